@@ -1,0 +1,203 @@
+"""Float64 oracle of the In-Place TTT layer (test infrastructure only).
+
+Sources (page titles and sections; the pages are web reviews of the paper):
+  * "In-Place Test-Time Training" review, Method §1 *Overall Framework*:
+    eq. (1) the gated MLP, eq. (2) the intermediate Z, the chunk split, and
+    the two per-chunk operations in order -- apply, eq. (3), then a gradient
+    step on the fast weight, eq. (4).
+  * same page, Method §2 *LM-Aligned Objective*: eq. (5) the target
+    V^ = Conv1D(X0) W_target, and eq. (6) the closed-form step under the
+    negative Frobenius inner-product loss.
+  * same page, Method §3 *Implementation Details*: the three-step parallel
+    form (all per-chunk deltas, one exclusive prefix sum, all applies), causal
+    padding of the convolution, and the reset of the fast weight at each
+    document boundary.
+  * "In-Place Test-Time Training" notes (gitcode), *implementation details*:
+    the same prefix-sum restatement.
+  * TTT-E2E summary, *mini-batch TTT*: the 1/b mean over a mini-batch, which
+    is the 1/C of the MSE objective here.
+
+Readings where the pages are open (each is listed with its reason in the
+design notes of the repository):
+  * phi is SiLU, silu(x) = x / (1 + exp(-x)).
+  * Conv1D is depthwise with weights conv_w[d, K] and no bias, left
+    zero-padded by K-1 ("causal padding"): tap K-1 multiplies the current
+    token, tap j multiplies the token K-1-j steps back.
+  * V^ = Y @ W_target with W_target indexed [d_in, d_out] (eq. (5) has no
+    transpose).
+  * Chunk c (0-based) is applied with the state left by chunks 0..c-1; chunk 0
+    uses W_down0; W_final includes the last chunk's update.
+  * dot objective: L = -<Z W^T, V^>_F, so the step is W + eta V^_c^T Z_c
+    (eq. (6), no 1/C).
+  * mse objective: L = (1/(2C)) ||Z_c W^T - V^_c||_F^2 at the pre-update W,
+    so the step is W - (eta/C)(Z_c W^T - V^_c)^T Z_c, with C the number of
+    tokens in that chunk.
+  * each batch row is one document with its own state starting at W_down0.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "silu", "causal_depthwise_conv1d", "target_values", "gated_intermediate",
+    "gated_mlp", "loss_dot", "loss_mse", "grad_dot", "grad_mse",
+    "chunk_apply_update", "chunk_prefix_form", "inplace_layer",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+def silu(x):
+    """SiLU (the reading of phi in eq. (1)): x * sigmoid(x)."""
+    x = _f64(x)
+    with np.errstate(over="ignore"):
+        return x / (1.0 + np.exp(-x))
+
+
+def causal_depthwise_conv1d(X0, conv_w):
+    """Causal depthwise 1-D convolution along the token axis (eq. (5), with the
+    causal padding of Method §3).
+
+    X0: [..., n, d]; conv_w: [d, K].  Y[t, ch] = sum_j conv_w[ch, j] *
+    X0[t - (K-1) + j, ch], where rows before the first token are zero.
+    """
+    X0 = _f64(X0)
+    conv_w = _f64(conv_w)
+    n = X0.shape[-2]
+    K = conv_w.shape[1]
+    Y = np.zeros_like(X0)
+    for j in range(K):
+        back = K - 1 - j          # tap j looks this many tokens back
+        if back >= n:
+            continue
+        Y[..., back:, :] += conv_w[:, j] * X0[..., : n - back, :]
+    return Y
+
+
+def target_values(X0, conv_w, W_target):
+    """V^ = Conv1D(X0) W_target (eq. (5)); W_target is [d_in, d_out]."""
+    return causal_depthwise_conv1d(X0, conv_w) @ _f64(W_target)
+
+
+def gated_intermediate(H, W_gate, W_up):
+    """Z = phi(H W_gate^T) * (H W_up^T) (eq. (2)); H [n, d], W_gate/W_up [f, d]."""
+    H = _f64(H)
+    return silu(H @ _f64(W_gate).T) * (H @ _f64(W_up).T)
+
+
+def gated_mlp(H, W_gate, W_up, W_down):
+    """The unmodified gated MLP of eq. (1): O = Z W_down^T, W_down [d, f]."""
+    return gated_intermediate(H, W_gate, W_up) @ _f64(W_down).T
+
+
+# --- the two objectives, as losses and as their gradients with respect to W ---
+
+def loss_dot(W, Zc, Vc):
+    """Negative Frobenius inner product between the chunk's output Z W^T and
+    its target (Method §2)."""
+    return -float(np.sum((_f64(Zc) @ _f64(W).T) * _f64(Vc)))
+
+
+def loss_mse(W, Zc, Vc):
+    """Mean-over-the-chunk squared reconstruction error, (1/(2C))||Z W^T - V||^2."""
+    Zc = _f64(Zc)
+    E = Zc @ _f64(W).T - _f64(Vc)
+    return float(0.5 * np.sum(E * E) / Zc.shape[0])
+
+
+def grad_dot(W, Zc, Vc):
+    """Gradient of loss_dot with respect to W [d, f]; independent of W."""
+    return -(_f64(Vc).T @ _f64(Zc))
+
+
+def grad_mse(W, Zc, Vc):
+    """Gradient of loss_mse with respect to W [d, f], at the given W."""
+    Zc = _f64(Zc)
+    return ((Zc @ _f64(W).T - _f64(Vc)).T @ Zc) / Zc.shape[0]
+
+
+_GRADS = {"dot": grad_dot, "mse": grad_mse}
+
+
+def chunk_apply_update(Z, Vhat, W0, chunk, eta, mode):
+    """The sequential definition (Method §1): for each chunk in order, apply the
+    current state (eq. (3)), then take one gradient step on it (eq. (4)).
+
+    Z [n, f], Vhat [n, d], W0 [d, f].  A last chunk shorter than `chunk` is
+    allowed here (it is simply the remaining tokens).
+    Returns (O [n, d], W_final [d, f]).
+    """
+    Z, Vhat = _f64(Z), _f64(Vhat)
+    W = _f64(W0).copy()
+    grad = _GRADS[mode]
+    n = Z.shape[0]
+    O = np.empty((n, W.shape[0]))
+    for start in range(0, n, chunk):
+        rows = slice(start, min(start + chunk, n))
+        O[rows] = Z[rows] @ W.T                       # apply: state before this chunk
+        W = W - eta * grad(W, Z[rows], Vhat[rows])     # update: gradient at that state
+    return O, W
+
+
+def chunk_prefix_form(Z, Vhat, W0, chunk, eta):
+    """The three-step parallel form of the dot-product update (Method §3):
+    (1) every chunk's delta V^_c^T Z_c, (2) one exclusive prefix sum over the
+    deltas, (3) every chunk applied with W0 + eta * (its prefix).
+    Returns (O [n, d], W_final [d, f])."""
+    Z, Vhat, W0 = _f64(Z), _f64(Vhat), _f64(W0)
+    n = Z.shape[0]
+    bounds = [(s, min(s + chunk, n)) for s in range(0, n, chunk)]
+    deltas = [Vhat[s:e].T @ Z[s:e] for (s, e) in bounds]           # step 1
+    prefix = [np.zeros_like(W0)]                                     # step 2
+    for dW in deltas:
+        prefix.append(prefix[-1] + dW)
+    O = np.empty((n, W0.shape[0]))
+    for c, (s, e) in enumerate(bounds):                              # step 3
+        O[s:e] = Z[s:e] @ (W0 + eta * prefix[c]).T
+    return O, W0 + eta * prefix[-1]
+
+
+def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
+                  mode, max_chunks=None, x0_halo=None):
+    """The whole In-Place TTT layer, one document per batch row.
+
+    H, X0 [B, n, d]; W_gate, W_up [f, d]; W_down0 [d, f]; W_target [d, d];
+    conv_w [d, K].  Streams chunk by chunk: Z_c and V^_c are formed for the
+    chunk only (the convolution reads the K-1 previous rows of X0, or
+    `x0_halo` [B, K-1, d] before the first row, else zeros).
+
+    `max_chunks` stops after that many chunks (O then covers only those rows
+    and W_final is the state after them) -- used to time a bounded sample.
+
+    Returns (O [B, n', d], W_final [B, d, f]).
+    """
+    H, X0 = _f64(H), _f64(X0)
+    W_gate, W_up, W_target, conv_w = map(_f64, (W_gate, W_up, W_target, conv_w))
+    B, n, d = H.shape
+    K = conv_w.shape[1]
+    grad = _GRADS[mode]
+    n_chunks = -(-n // chunk) if n else 0
+    if max_chunks is not None:
+        n_chunks = min(n_chunks, max_chunks)
+    n_out = min(n, n_chunks * chunk)
+    O = np.empty((B, n_out, d))
+    W_final = np.empty((B, d, W_gate.shape[0]))
+    for b in range(B):
+        if x0_halo is not None:
+            Xfull = np.concatenate([_f64(x0_halo[b]), X0[b]], axis=0)
+            off = K - 1
+        else:
+            Xfull, off = X0[b], 0
+        W = _f64(W_down0).copy()       # document boundary: reset to the pretrained state
+        for c in range(n_chunks):
+            s, e = c * chunk, min((c + 1) * chunk, n)
+            lo = max(0, s + off - (K - 1))
+            Y = causal_depthwise_conv1d(Xfull[lo: e + off], conv_w)[-(e - s):]
+            Vc = Y @ W_target
+            Zc = gated_intermediate(H[b, s:e], W_gate, W_up)
+            O[b, s:e] = Zc @ W.T
+            W = W - eta * grad(W, Zc, Vc)
+        W_final[b] = W
+    return O, W_final

@@ -1,0 +1,88 @@
+"""Float64 oracle of the LaCT SwiGLU fast-weight layer (test infrastructure only).
+
+Sources: "Test-Time Training Done Right" review --
+  * Preliminary §1, eq. (1): the update W <- W - eta grad L(f_W(k), v) and
+    the apply o = f_W(q), with L usually the squared error;
+  * LaCT Model Architecture §1, eq. (3): one gradient per chunk, of the loss
+    summed over the chunk's tokens; all queries of the chunk share the
+    updated weights; eq. (4): f_W(x) = W2 [SiLU(W1 x) * (W3 x)], no bias;
+  * the same section, on ordering: update-then-apply within a chunk versus
+    apply-then-update.
+"ViT^3" review, Insight 2 and 3: one full-batch GD step per chunk, eta = 1.
+
+Readings: the per-token loss is (1/2)||f_W(k_i) - v_i||^2, summed (no mean)
+over the chunk; scalar eta; plain simultaneous GD on W1, W3, W2 (no weight
+normalisation, no Muon); layout q, k, v [B, H, n, dh], W1, W3 [H, m, dh],
+W2 [H, dh, m], every (batch row, head) with its own state.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .inplace import silu
+
+__all__ = ["swiglu_apply", "swiglu_loss", "swiglu_grads", "lact_layer"]
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def swiglu_apply(x, W1, W3, W2):
+    """f_W(x) row-wise (eq. (4)): x [C, dh] -> [C, dh]."""
+    x = _f64(x)
+    return (silu(x @ _f64(W1).T) * (x @ _f64(W3).T)) @ _f64(W2).T
+
+
+def swiglu_loss(kc, vc, W1, W3, W2):
+    """Chunk loss: sum over tokens of (1/2)||f_W(k_i) - v_i||^2."""
+    R = swiglu_apply(kc, W1, W3, W2) - _f64(vc)
+    return float(0.5 * np.sum(R * R))
+
+
+def swiglu_grads(kc, vc, W1, W3, W2):
+    """Gradients (G1, G3, G2) of swiglu_loss with respect to W1, W3, W2,
+    by the chain rule written out by hand."""
+    kc, vc, W1, W3, W2 = map(_f64, (kc, vc, W1, W3, W2))
+    A = kc @ W1.T                     # [C, m]
+    U = kc @ W3.T                     # [C, m]
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-A))
+    S = A * sig                       # silu(A)
+    Hh = S * U                        # hidden [C, m]
+    R = Hh @ W2.T - vc                # residual [C, dh]
+    G2 = R.T @ Hh                     # [dh, m]
+    dH = R @ W2                       # [C, m]
+    dU = dH * S
+    dA = dH * U * (sig * (1.0 + A * (1.0 - sig)))   # silu'(a) = sig(a)(1 + a(1 - sig(a)))
+    G3 = dU.T @ kc                    # [m, dh]
+    G1 = dA.T @ kc                    # [m, dh]
+    return G1, G3, G2
+
+
+def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply"):
+    """LaCT layer over chunks.  q, k, v [B, H, n, dh]; W1, W3 [H, m, dh];
+    W2 [H, dh, m].  Returns (O [B, H, n, dh], W1_f, W3_f [B, H, m, dh],
+    W2_f [B, H, dh, m])."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
+    B, Hn, n, dh = q.shape
+    O = np.empty_like(q)
+    W1f = np.empty((B,) + W1.shape)
+    W3f = np.empty((B,) + W3.shape)
+    W2f = np.empty((B,) + W2.shape)
+    for b in range(B):
+        for h in range(Hn):
+            w1, w3, w2 = W1[h].copy(), W3[h].copy(), W2[h].copy()
+            for s in range(0, n, chunk):
+                r = slice(s, min(s + chunk, n))
+                if order == "apply_then_update":
+                    O[b, h, r] = swiglu_apply(q[b, h, r], w1, w3, w2)
+                g1, g3, g2 = swiglu_grads(k[b, h, r], v[b, h, r], w1, w3, w2)
+                w1, w3, w2 = w1 - eta * g1, w3 - eta * g3, w2 - eta * g2
+                if order == "update_then_apply":
+                    O[b, h, r] = swiglu_apply(q[b, h, r], w1, w3, w2)
+                elif order != "apply_then_update":
+                    raise ValueError(f"unknown order {order!r}")
+            W1f[b, h], W3f[b, h], W2f[b, h] = w1, w3, w2
+    return O, W1f, W3f, W2f

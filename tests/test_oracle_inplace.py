@@ -1,0 +1,397 @@
+"""Pins of the In-Place TTT oracle against things other than itself.
+
+Each test fixes the oracle to a library routine, a hand-derived fixture, a
+closed form, a brute force written a different way, finite differences of
+the loss definitions, or an invariant the pages state.  All run on the CPU.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import inplace as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as fh:
+        return json.load(fh)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _problem(rng, n, d, f, K=4):
+    H = rng.standard_normal((n, d))
+    X0 = rng.standard_normal((n, d))
+    Wg = rng.standard_normal((f, d)) / np.sqrt(d)
+    Wu = rng.standard_normal((f, d)) / np.sqrt(d)
+    W0 = rng.standard_normal((d, f)) / np.sqrt(f)
+    Wt = rng.standard_normal((d, d)) / np.sqrt(d)
+    cw = rng.standard_normal((d, K)) * 0.5
+    return H, X0, Wg, Wu, W0, Wt, cw
+
+
+# ---------------------------------------------------------------- conv / producers
+
+def test_conv_golden_hand_derived():
+    g = _golden("conv_tiny.json")
+    Y = orc.causal_depthwise_conv1d(np.array(g["X0"]), np.array(g["conv_w"]))
+    np.testing.assert_array_equal(Y, np.array(g["Y"], dtype=np.float64))
+
+
+@pytest.mark.parametrize("n,d,K", [(17, 5, 4), (3, 4, 4), (9, 3, 1), (6, 2, 7)])
+def test_conv_matches_torch_conv1d(n, d, K):
+    rng = _rng(n * 100 + K)
+    X0 = rng.standard_normal((2, n, d))
+    w = rng.standard_normal((d, K))
+    ref = F.conv1d(torch.from_numpy(X0).transpose(1, 2), torch.from_numpy(w)[:, None, :],
+                   groups=d, padding=K - 1)[..., :n].transpose(1, 2).numpy()
+    np.testing.assert_allclose(orc.causal_depthwise_conv1d(X0, w), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_conv_identity_tap_reduces_to_x0():
+    # a one-hot kernel on the current-token tap with W_target = I gives V^ = X0
+    rng = _rng(3)
+    X0 = rng.standard_normal((11, 6))
+    w = np.zeros((6, 4))
+    w[:, 3] = 1.0
+    np.testing.assert_array_equal(orc.target_values(X0, w, np.eye(6)), X0)
+    # one-hot one step back: the previous token (zero at t = 0)
+    w = np.zeros((6, 4))
+    w[:, 2] = 1.0
+    V = orc.target_values(X0, w, np.eye(6))
+    np.testing.assert_array_equal(V[1:], X0[:-1])
+    np.testing.assert_array_equal(V[0], 0.0)
+
+
+def test_target_orientation_is_din_dout():
+    rng = _rng(4)
+    X0 = rng.standard_normal((5, 3))
+    w = np.zeros((3, 4))
+    w[:, 3] = 1.0
+    Wt = rng.standard_normal((3, 7))         # non-square: only Y @ Wt is defined
+    assert orc.target_values(X0, w, Wt).shape == (5, 7)
+    np.testing.assert_allclose(orc.target_values(X0, w, Wt), X0 @ Wt, rtol=1e-14)
+
+
+def test_gated_intermediate_matches_torch():
+    rng = _rng(5)
+    H = rng.standard_normal((13, 8))
+    Wg = rng.standard_normal((11, 8))
+    Wu = rng.standard_normal((11, 8))
+    Ht = torch.from_numpy(H)
+    ref = (F.silu(F.linear(Ht, torch.from_numpy(Wg))) * F.linear(Ht, torch.from_numpy(Wu))).numpy()
+    np.testing.assert_allclose(orc.gated_intermediate(H, Wg, Wu), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_silu_special_values():
+    np.testing.assert_array_equal(orc.silu(np.array([0.0])), [0.0])
+    np.testing.assert_allclose(orc.silu(np.array([50.0, -50.0])), [50.0, -50.0 * np.exp(-50.0)], rtol=1e-12)
+    np.testing.assert_allclose(orc.silu(np.array([1.0])), [1.0 / (1.0 + np.exp(-1.0))], rtol=1e-15)
+    assert np.isfinite(orc.silu(np.array([-1000.0]))).all()
+
+
+# ---------------------------------------------------------------- hand-derived recursions
+
+@pytest.mark.parametrize("name", ["scalar_dot.json", "scalar_mse.json", "matrix_dot.json"])
+def test_chunk_loop_golden(name):
+    g = _golden(name)
+    O, W = orc.chunk_apply_update(np.array(g["Z"], float), np.array(g["Vhat"], float),
+                                  np.array(g["W0"], float), g["chunk"], g["eta"], g["mode"])
+    np.testing.assert_allclose(O, np.array(g["O"], float), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(W, np.array(g["W_final"], float), rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------- brute force
+
+def _dual_form_dot(Z, V, W0, C, eta):
+    """Token-by-token dual form written with explicit loops: the output of token
+    t is Z_t W0^T plus eta times the sum over every token s of an earlier chunk
+    of (Z_t . Z_s) V_s.  No prefix sums, no matrix state."""
+    n, f = Z.shape
+    d = V.shape[1]
+    O = np.zeros((n, d))
+    for t in range(n):
+        for i in range(d):
+            acc = 0.0
+            for j in range(f):
+                acc += Z[t, j] * W0[i, j]
+            O[t, i] = acc
+        for s in range(n):
+            if s // C < t // C:
+                dot = sum(Z[t, j] * Z[s, j] for j in range(f))
+                for i in range(d):
+                    O[t, i] += eta * dot * V[s, i]
+    Wf = W0.copy()
+    for s in range(n):
+        for i in range(d):
+            for j in range(f):
+                Wf[i, j] += eta * V[s, i] * Z[s, j]
+    return O, Wf
+
+
+@pytest.mark.parametrize("n,C", [(12, 4), (12, 1), (12, 12), (10, 4), (7, 3)])
+def test_dot_equals_block_causal_dual_brute_force(n, C):
+    rng = _rng(n * 31 + C)
+    d, f = 3, 5
+    Z = rng.standard_normal((n, f))
+    V = rng.standard_normal((n, d))
+    W0 = rng.standard_normal((d, f))
+    O, W = orc.chunk_apply_update(Z, V, W0, C, 0.3, "dot")
+    Ob, Wb = _dual_form_dot(Z, V, W0, C, 0.3)
+    np.testing.assert_allclose(O, Ob, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(W, Wb, rtol=1e-12, atol=1e-12)
+
+
+def _online_gd_mse(Z, V, W0, eta):
+    """Per-token TTT with the squared error (chunk of one token), scalar loops."""
+    n, f = Z.shape
+    d = V.shape[1]
+    W = W0.copy()
+    O = np.zeros((n, d))
+    for t in range(n):
+        for i in range(d):
+            O[t, i] = sum(W[i, j] * Z[t, j] for j in range(f))
+        for i in range(d):
+            e = O[t, i] - V[t, i]
+            for j in range(f):
+                W[i, j] -= eta * e * Z[t, j]
+    return O, W
+
+
+def test_mse_chunk_one_is_per_token_online_gd():
+    rng = _rng(7)
+    Z = rng.standard_normal((9, 4)) * 0.5
+    V = rng.standard_normal((9, 3))
+    W0 = rng.standard_normal((3, 4))
+    O, W = orc.chunk_apply_update(Z, V, W0, 1, 0.2, "mse")
+    Ob, Wb = _online_gd_mse(Z, V, W0, 0.2)
+    np.testing.assert_allclose(O, Ob, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(W, Wb, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- gradients by finite differences
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_gradients_match_finite_differences(mode):
+    rng = _rng(11)
+    C, d, f = 6, 3, 4
+    Z = rng.standard_normal((C, f))
+    V = rng.standard_normal((C, d))
+    W = rng.standard_normal((d, f))
+    loss = {"dot": orc.loss_dot, "mse": orc.loss_mse}[mode]
+    grad = {"dot": orc.grad_dot, "mse": orc.grad_mse}[mode](W, Z, V)
+    h = 1e-6
+    fd = np.zeros_like(W)
+    for i in range(d):
+        for j in range(f):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[i, j] += h
+            Wm[i, j] -= h
+            fd[i, j] = (loss(Wp, Z, V) - loss(Wm, Z, V)) / (2 * h)
+    np.testing.assert_allclose(grad, fd, rtol=1e-7, atol=1e-8)
+
+
+def test_gradients_match_autograd():
+    rng = _rng(12)
+    C, d, f = 5, 4, 6
+    Z = torch.from_numpy(rng.standard_normal((C, f)))
+    V = torch.from_numpy(rng.standard_normal((C, d)))
+    W = torch.from_numpy(rng.standard_normal((d, f))).requires_grad_(True)
+    (-(Z @ W.T * V).sum()).backward()
+    np.testing.assert_allclose(orc.grad_dot(W.detach().numpy(), Z.numpy(), V.numpy()), W.grad.numpy(), rtol=1e-13)
+    W.grad = None
+    (((Z @ W.T - V) ** 2).sum() / (2 * C)).backward()
+    np.testing.assert_allclose(orc.grad_mse(W.detach().numpy(), Z.numpy(), V.numpy()), W.grad.numpy(), rtol=1e-12)
+
+
+# ---------------------------------------------------------------- special cases
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_eta_zero_is_plain_gated_mlp(mode):
+    rng = _rng(13)
+    H, X0, Wg, Wu, W0, Wt, cw = _problem(rng, 24, 6, 10)
+    O, Wf = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, 8, 0.0, mode)
+    ref = (F.silu(torch.from_numpy(H) @ torch.from_numpy(Wg).T) * (torch.from_numpy(H) @ torch.from_numpy(Wu).T)) \
+        @ torch.from_numpy(W0).T
+    np.testing.assert_allclose(O[0], ref.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(Wf[0], W0)
+
+
+def test_chunk_equal_sequence_is_one_full_batch_step():
+    rng = _rng(14)
+    n, d, f = 16, 4, 7
+    Z = rng.standard_normal((n, f))
+    V = rng.standard_normal((n, d))
+    W0 = rng.standard_normal((d, f))
+    O, W = orc.chunk_apply_update(Z, V, W0, n, 0.25, "dot")
+    np.testing.assert_allclose(O, np.einsum("tf,df->td", Z, W0), rtol=1e-13)
+    np.testing.assert_allclose(W, W0 + 0.25 * np.einsum("ti,tj->ij", V, Z), rtol=1e-13)
+    O, W = orc.chunk_apply_update(Z, V, W0, n, 0.25, "mse")
+    E = np.einsum("tf,df->td", Z, W0) - V
+    np.testing.assert_allclose(O, np.einsum("tf,df->td", Z, W0), rtol=1e-13)
+    np.testing.assert_allclose(W, W0 - 0.25 / n * np.einsum("ti,tj->ij", E, Z), rtol=1e-13)
+
+
+def test_mse_orthogonal_keys_reach_target_in_one_step():
+    # chunk = d_ff, Z = sqrt(C) Q with Q orthogonal, V^ = Z W*^T, eta = 1:
+    # W - (1/C)(W - W*) Z^T Z = W*
+    rng = _rng(15)
+    f, d = 8, 5
+    Q, _ = np.linalg.qr(rng.standard_normal((f, f)))
+    Z = np.sqrt(f) * Q
+    Wstar = rng.standard_normal((d, f))
+    V = Z @ Wstar.T
+    W0 = rng.standard_normal((d, f))
+    _, W = orc.chunk_apply_update(Z, V, W0, f, 1.0, "mse")
+    np.testing.assert_allclose(W, Wstar, rtol=1e-12, atol=1e-12)
+
+
+def test_mse_eta_scaling_identity():
+    # eta * K^T (K W - V) = K~^T (K~ W - V~) with K~ = sqrt(eta) K, V~ = sqrt(eta) V
+    rng = _rng(16)
+    Z = rng.standard_normal((12, 5))
+    V = rng.standard_normal((12, 3))
+    W0 = rng.standard_normal((3, 5))
+    eta = 0.37
+    O1, W1 = orc.chunk_apply_update(Z, V, W0, 4, eta, "mse")
+    O2, W2 = orc.chunk_apply_update(np.sqrt(eta) * Z, np.sqrt(eta) * V, W0, 4, 1.0, "mse")
+    np.testing.assert_allclose(W1, W2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(O1 * np.sqrt(eta), O2, rtol=1e-12, atol=1e-13)
+
+
+def test_prefix_form_equals_sequential():
+    rng = _rng(17)
+    for n, C in [(32, 8), (30, 8), (5, 5), (9, 1)]:
+        Z = rng.standard_normal((n, 6))
+        V = rng.standard_normal((n, 4))
+        W0 = rng.standard_normal((4, 6))
+        O1, W1 = orc.chunk_apply_update(Z, V, W0, C, 0.05, "dot")
+        O2, W2 = orc.chunk_prefix_form(Z, V, W0, C, 0.05)
+        np.testing.assert_allclose(O1, O2, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(W1, W2, rtol=1e-12, atol=1e-12)
+
+
+def test_dot_is_affine_in_eta():
+    rng = _rng(18)
+    Z = rng.standard_normal((20, 6))
+    V = rng.standard_normal((20, 4))
+    W0 = rng.standard_normal((4, 6))
+    O0, _ = orc.chunk_apply_update(Z, V, W0, 5, 0.0, "dot")
+    O1, _ = orc.chunk_apply_update(Z, V, W0, 5, 0.1, "dot")
+    O2, _ = orc.chunk_apply_update(Z, V, W0, 5, 0.2, "dot")
+    np.testing.assert_allclose(O2 - 2 * O1 + O0, 0.0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- causality, batch, resume
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_causality_future_targets_do_not_reach_past_chunks(mode):
+    rng = _rng(19)
+    n, C, d, f = 32, 8, 4, 6
+    H, X0, Wg, Wu, W0, Wt, cw = _problem(rng, n, d, f)
+    O, _ = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, C, 0.1, mode)
+    for c in range(n // C):
+        X0p = X0.copy()
+        X0p[c * C:] += rng.standard_normal(X0p[c * C:].shape)     # changes V^ of chunks >= c
+        Hp = H.copy()
+        Hp[(c + 1) * C:] += rng.standard_normal(Hp[(c + 1) * C:].shape)  # changes Z of chunks > c
+        Op, _ = orc.inplace_layer(Hp[None], X0p[None], Wg, Wu, W0, Wt, cw, C, 0.1, mode)
+        np.testing.assert_array_equal(Op[0, : (c + 1) * C], O[0, : (c + 1) * C])
+        if c + 1 < n // C:
+            assert not np.array_equal(Op[0, (c + 1) * C:], O[0, (c + 1) * C:])
+
+
+def test_layer_batch_rows_are_independent_documents():
+    rng = _rng(20)
+    n, C, d, f = 16, 4, 3, 5
+    H = rng.standard_normal((3, n, d))
+    X0 = rng.standard_normal((3, n, d))
+    _, _, Wg, Wu, W0, Wt, cw = _problem(rng, n, d, f)
+    O, Wf = orc.inplace_layer(H, X0, Wg, Wu, W0, Wt, cw, C, 0.2, "dot")
+    for b in range(3):
+        Ob, Wb = orc.inplace_layer(H[b:b + 1], X0[b:b + 1], Wg, Wu, W0, Wt, cw, C, 0.2, "dot")
+        np.testing.assert_array_equal(O[b], Ob[0])
+        np.testing.assert_array_equal(Wf[b], Wb[0])
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_resume_at_chunk_boundary_with_conv_halo(mode):
+    rng = _rng(21)
+    n, C, d, f, K = 24, 6, 4, 5, 4
+    H, X0, Wg, Wu, W0, Wt, cw = _problem(rng, n, d, f, K)
+    O, Wf = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, C, 0.1, mode)
+    s = 2 * C
+    O1, W1 = orc.inplace_layer(H[None, :s], X0[None, :s], Wg, Wu, W0, Wt, cw, C, 0.1, mode)
+    O2, W2 = orc.inplace_layer(H[None, s:], X0[None, s:], Wg, Wu, W1[0], Wt, cw, C, 0.1, mode,
+                               x0_halo=X0[None, s - (K - 1): s])
+    np.testing.assert_allclose(np.concatenate([O1, O2], axis=1), O, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(W2, Wf, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_matches_whole_sequence_composition():
+    # streaming per chunk must equal forming Z and V^ over the whole sequence first
+    rng = _rng(22)
+    n, C, d, f = 40, 8, 5, 7
+    H, X0, Wg, Wu, W0, Wt, cw = _problem(rng, n, d, f)
+    Z = orc.gated_intermediate(H, Wg, Wu)
+    V = orc.target_values(X0, cw, Wt)
+    for mode in ("dot", "mse"):
+        O, Wf = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, C, 0.05, mode)
+        O2, W2 = orc.chunk_apply_update(Z, V, W0, C, 0.05, mode)
+        np.testing.assert_allclose(O[0], O2, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(Wf[0], W2, rtol=1e-12, atol=1e-12)
+
+
+def test_max_chunks_gives_the_prefix_of_the_run():
+    rng = _rng(23)
+    n, C, d, f = 32, 8, 3, 4
+    H, X0, Wg, Wu, W0, Wt, cw = _problem(rng, n, d, f)
+    O, _ = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, C, 0.1, "mse")
+    Op, Wp = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, C, 0.1, "mse", max_chunks=2)
+    _, W2 = orc.inplace_layer(H[None, : 2 * C], X0[None, : 2 * C], Wg, Wu, W0, Wt, cw, C, 0.1, "mse")
+    np.testing.assert_array_equal(Op[0], O[0, : 2 * C])
+    np.testing.assert_array_equal(Wp, W2)
+
+
+def test_empty_sequence():
+    rng = _rng(24)
+    _, _, Wg, Wu, W0, Wt, cw = _problem(rng, 4, 3, 5)
+    O, Wf = orc.inplace_layer(np.zeros((2, 0, 3)), np.zeros((2, 0, 3)), Wg, Wu, W0, Wt, cw, 4, 0.1, "dot")
+    assert O.shape == (2, 0, 3)
+    np.testing.assert_array_equal(Wf, np.broadcast_to(W0, (2, 3, 5)))
+
+
+# ---------------------------------------------------------------- planted mistakes must be caught
+
+def test_planted_mistakes_fail_the_pins(monkeypatch):
+    """Each plausible mistake (inclusive prefix, wrong sign, missing 1/C,
+    transposed target) makes at least one pin fail."""
+    g = _golden("matrix_dot.json")
+    Z, V, W0 = (np.array(g[k], float) for k in ("Z", "Vhat", "W0"))
+
+    def inclusive(Z, V, W0, chunk, eta, mode):
+        W = W0.copy()
+        O = np.empty((Z.shape[0], W0.shape[0]))
+        for s in range(0, Z.shape[0], chunk):
+            r = slice(s, s + chunk)
+            W = W + eta * V[r].T @ Z[r]
+            O[r] = Z[r] @ W.T
+        return O, W
+    O, _ = inclusive(Z, V, W0, g["chunk"], g["eta"], "dot")
+    assert not np.allclose(O, np.array(g["O"], float))
+
+    O, W = orc.chunk_apply_update(Z, -V, W0, g["chunk"], g["eta"], "dot")   # wrong sign
+    assert not np.allclose(W, np.array(g["W_final"], float))
+
+    gm = _golden("scalar_mse.json")
+    Zs, Vs, Ws = (np.array(gm[k], float) for k in ("Z", "Vhat", "W0"))
+    monkeypatch.setitem(orc._GRADS, "mse", lambda W, Zc, Vc: (Zc @ W.T - Vc).T @ Zc)  # no 1/C
+    _, W = orc.chunk_apply_update(Zs, Vs, Ws, gm["chunk"], gm["eta"], "mse")
+    assert not np.allclose(W, np.array(gm["W_final"], float))

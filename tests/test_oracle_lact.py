@@ -1,0 +1,137 @@
+"""Pins of the LaCT SwiGLU oracle: autograd, finite differences, a hand-derived
+scalar case, eta = 0, chunk = sequence, and causality of the ordering."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import lact as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _problem(seed, B=1, H=2, n=12, dh=3, m=5):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, n, dh))
+    k = rng.standard_normal((B, H, n, dh))
+    v = rng.standard_normal((B, H, n, dh))
+    W1 = rng.standard_normal((H, m, dh)) / np.sqrt(dh)
+    W3 = rng.standard_normal((H, m, dh)) / np.sqrt(dh)
+    W2 = rng.standard_normal((H, dh, m)) / np.sqrt(m)
+    return q, k, v, W1, W3, W2
+
+
+def _torch_swiglu(x, W1, W3, W2):
+    return F.linear(F.silu(F.linear(x, W1)) * F.linear(x, W3), W2)
+
+
+def test_grads_match_autograd():
+    q, k, v, W1, W3, W2 = _problem(1, n=9, dh=4, m=6)
+    kc, vc = k[0, 0], v[0, 0]
+    w1, w3, w2 = (torch.from_numpy(a[0].copy()).requires_grad_(True) for a in (W1, W3, W2))
+    out = _torch_swiglu(torch.from_numpy(kc), w1, w3, w2)
+    (0.5 * ((out - torch.from_numpy(vc)) ** 2).sum()).backward()
+    G1, G3, G2 = orc.swiglu_grads(kc, vc, W1[0], W3[0], W2[0])
+    np.testing.assert_allclose(G1, w1.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(G3, w3.grad.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(G2, w2.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_grads_match_finite_differences():
+    q, k, v, W1, W3, W2 = _problem(2, n=5, dh=2, m=3)
+    kc, vc = k[0, 0], v[0, 0]
+    Ws = [W1[0].copy(), W3[0].copy(), W2[0].copy()]
+    grads = orc.swiglu_grads(kc, vc, *Ws)
+    h = 1e-6
+    for which in range(3):
+        fd = np.zeros_like(Ws[which])
+        for idx in np.ndindex(*Ws[which].shape):
+            Wp = [w.copy() for w in Ws]
+            Wm = [w.copy() for w in Ws]
+            Wp[which][idx] += h
+            Wm[which][idx] -= h
+            fd[idx] = (orc.swiglu_loss(kc, vc, *Wp) - orc.swiglu_loss(kc, vc, *Wm)) / (2 * h)
+        np.testing.assert_allclose(grads[which], fd, rtol=1e-6, atol=1e-8)
+
+
+def test_scalar_golden_hand_derived():
+    with open(os.path.join(GOLDEN, "lact_scalar.json")) as fh:
+        g = json.load(fh)
+    a = lambda x: np.array([[x]], dtype=np.float64)
+    G1, G3, G2 = orc.swiglu_grads(a(g["k"]), a(g["v"]), a(g["w1"]), a(g["w3"]), a(g["w2"]))
+    assert G1.item() == g["G1"] and G3.item() == g["G3"] and G2.item() == g["G2"]
+    q = np.array(g["q"]).reshape(1, 1, 1, 1)
+    k = np.array(g["k"]).reshape(1, 1, 1, 1)
+    v = np.array(g["v"]).reshape(1, 1, 1, 1)
+    O, W1f, W3f, W2f = orc.lact_layer(q, k, v, a(g["w1"])[None], a(g["w3"])[None], a(g["w2"])[None],
+                                      1, g["eta"], "update_then_apply")
+    assert W1f.item() == g["w1_after"] and W3f.item() == g["w3_after"] and W2f.item() == g["w2_after"]
+    np.testing.assert_allclose(O.item(), 144.0 / (1.0 + math.exp(-12.0)), rtol=1e-15)
+
+
+@pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
+def test_eta_zero_is_plain_swiglu(order):
+    q, k, v, W1, W3, W2 = _problem(3)
+    O, W1f, W3f, W2f = orc.lact_layer(q, k, v, W1, W3, W2, 4, 0.0, order)
+    for h in range(W1.shape[0]):
+        ref = _torch_swiglu(torch.from_numpy(q[0, h]), torch.from_numpy(W1[h]), torch.from_numpy(W3[h]),
+                            torch.from_numpy(W2[h])).numpy()
+        np.testing.assert_allclose(O[0, h], ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(W1f[0], W1)
+    np.testing.assert_array_equal(W2f[0], W2)
+
+
+def test_chunk_equal_sequence_is_one_full_batch_gd_step():
+    q, k, v, W1, W3, W2 = _problem(4, H=1, n=10)
+    eta = 0.7
+    O, W1f, W3f, W2f = orc.lact_layer(q, k, v, W1, W3, W2, 10, eta, "update_then_apply")
+    w1, w3, w2 = (torch.from_numpy(a[0].copy()).requires_grad_(True) for a in (W1, W3, W2))
+    loss = 0.5 * ((_torch_swiglu(torch.from_numpy(k[0, 0]), w1, w3, w2) - torch.from_numpy(v[0, 0])) ** 2).sum()
+    loss.backward()
+    n1, n3, n2 = (w.detach() - eta * w.grad for w in (w1, w3, w2))
+    np.testing.assert_allclose(W1f[0, 0], n1.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(W3f[0, 0], n3.numpy(), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(W2f[0, 0], n2.numpy(), rtol=1e-12, atol=1e-14)
+    ref = _torch_swiglu(torch.from_numpy(q[0, 0]), n1, n3, n2).numpy()
+    np.testing.assert_allclose(O[0, 0], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_update_then_apply_causality():
+    q, k, v, W1, W3, W2 = _problem(5, n=16)
+    C = 4
+    O, *_ = orc.lact_layer(q, k, v, W1, W3, W2, C, 0.5, "update_then_apply")
+    rng = np.random.default_rng(50)
+    for c in range(4):
+        kp, vp, qp = k.copy(), v.copy(), q.copy()
+        kp[:, :, (c + 1) * C:] += rng.standard_normal(kp[:, :, (c + 1) * C:].shape)
+        vp[:, :, (c + 1) * C:] += rng.standard_normal(vp[:, :, (c + 1) * C:].shape)
+        qp[:, :, (c + 1) * C:] += rng.standard_normal(qp[:, :, (c + 1) * C:].shape)
+        Op, *_ = orc.lact_layer(qp, kp, vp, W1, W3, W2, C, 0.5, "update_then_apply")
+        np.testing.assert_array_equal(Op[:, :, : (c + 1) * C], O[:, :, : (c + 1) * C])
+    # within a chunk, the chunk's own keys reach its queries (update first)
+    kp = k.copy()
+    kp[:, :, 0] += 1.0
+    Op, *_ = orc.lact_layer(q, kp, v, W1, W3, W2, C, 0.5, "update_then_apply")
+    assert not np.allclose(Op[:, :, :C], O[:, :, :C])
+
+
+def test_apply_then_update_first_chunk_uses_initial_weights():
+    q, k, v, W1, W3, W2 = _problem(6, n=8)
+    O, *_ = orc.lact_layer(q, k, v, W1, W3, W2, 4, 0.5, "apply_then_update")
+    for h in range(2):
+        np.testing.assert_allclose(O[0, h, :4], orc.swiglu_apply(q[0, h, :4], W1[h], W3[h], W2[h]), rtol=1e-14)
+
+
+def test_heads_and_batch_rows_are_independent():
+    q, k, v, W1, W3, W2 = _problem(7, B=2, H=2, n=8)
+    O, W1f, _, _ = orc.lact_layer(q, k, v, W1, W3, W2, 4, 0.3)
+    for b in range(2):
+        for h in range(2):
+            Ob, W1b, _, _ = orc.lact_layer(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                           W1[h:h + 1], W3[h:h + 1], W2[h:h + 1], 4, 0.3)
+            np.testing.assert_array_equal(O[b, h], Ob[0, 0])
+            np.testing.assert_array_equal(W1f[b, h], W1b[0, 0])

@@ -1,0 +1,193 @@
+"""Seeded synthetic inputs for the chunk-wise TTT fast-weight layer.
+
+This module holds no arithmetic of the method: it only draws tensors.  Both
+the oracle side (tests, CPU baseline) and the HIP side (tests, bench) take
+their inputs from here, so that the two see bit-identical values.
+
+Recipe (for every workload):
+  * a ``torch.Generator`` on the CPU, seeded with ``seed``;
+  * tensors are drawn in a fixed order with ``torch.randn`` in fp32, scaled
+    by the stated standard deviation (the workloads give variances: N(0, x)
+    means variance x, std sqrt(x));
+  * for bf16 workloads the fp32 draw is rounded once to bf16 with
+    round-to-nearest-even (torch's float->bfloat16 conversion);
+  * the LaCT q, k, v are L2-normalised per token per head in fp32 *before*
+    the bf16 rounding (input preparation, not part of the layer).
+
+Draw order, In-Place layer: H, X0, W_gate, W_up, W_down0, W_target, conv_w.
+Draw order, LaCT layer: q, k, v, W1, W3, W2.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+__all__ = [
+    "InplaceConfig", "LactConfig", "WORKLOADS", "workload",
+    "inplace_inputs", "lact_inputs", "to_f64", "bf16_round",
+]
+
+
+@dataclass(frozen=True)
+class InplaceConfig:
+    """Shape and hyper-parameters of one In-Place TTT layer call."""
+    name: str
+    batch: int
+    seq_len: int
+    d_model: int
+    d_ff: int
+    chunk: int
+    eta: float
+    mode: str            # "dot" (prefix-sum update) or "mse" (sequential scan)
+    dtype: str           # "f32" or "bf16"
+    conv_k: int = 4
+    seed: int = 1000
+    # variances of the Gaussian draws; None means "use the default"
+    var_h: float = 1.0
+    var_x0: float = 1.0
+    var_gate: float | None = None    # default 1/d_model
+    var_up: float | None = None      # default 1/d_model
+    var_down: float | None = None    # default 1/d_ff
+    var_target: float | None = None  # default 1/d_model
+    var_conv: float = 0.25
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seq_len
+
+    @property
+    def n_chunks(self) -> int:
+        return self.seq_len // self.chunk
+
+    def flops(self) -> float:
+        """Algorithmic flops of one layer call: producer 4df, target 2d^2 + 2Kd,
+        update 2df, apply 2df per token."""
+        d, f, K = self.d_model, self.d_ff, self.conv_k
+        return float(self.tokens) * (8.0 * d * f + 2.0 * d * d + 2.0 * K * d)
+
+    def with_(self, **kw) -> "InplaceConfig":
+        return replace(self, **kw)
+
+
+@dataclass(frozen=True)
+class LactConfig:
+    """Shape and hyper-parameters of one LaCT SwiGLU fast-weight layer call."""
+    name: str
+    batch: int
+    heads: int
+    seq_len: int
+    head_dim: int
+    hidden: int
+    chunk: int
+    eta: float
+    order: str = "update_then_apply"   # or "apply_then_update"
+    dtype: str = "bf16"
+    seed: int = 1004
+    var_w1: float | None = None   # default 1/head_dim
+    var_w3: float | None = None   # default 1/head_dim
+    var_w2: float | None = None   # default 1/hidden
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seq_len
+
+    @property
+    def n_chunks(self) -> int:
+        return self.seq_len // self.chunk
+
+    def flops(self) -> float:
+        """Algorithmic flops: per token per head, key forward 6*dh*m,
+        backward 8*dh*m (dH, G1, G2, G3), query apply 6*dh*m."""
+        return float(self.tokens) * self.heads * 20.0 * self.head_dim * self.hidden
+
+    def with_(self, **kw) -> "LactConfig":
+        return replace(self, **kw)
+
+
+# The five workloads (and the chunk-512 variant of the 128K one).
+WORKLOADS = {
+    "inplace_f32_2k": InplaceConfig("inplace_f32_2k", 1, 2048, 256, 512, 256, 0.1, "dot", "f32", seed=1000),
+    "inplace_bf16_32k": InplaceConfig("inplace_bf16_32k", 1, 32768, 2560, 9728, 1024, 0.01, "dot", "bf16", seed=1001),
+    "inplace_bf16_128k": InplaceConfig("inplace_bf16_128k", 1, 131072, 2560, 9728, 4096, 0.01, "dot", "bf16", seed=1002),
+    "inplace_bf16_128k_c512": InplaceConfig("inplace_bf16_128k_c512", 1, 131072, 2560, 9728, 512, 0.01, "dot", "bf16", seed=1002),
+    "mse_bf16_4x64k": InplaceConfig("mse_bf16_4x64k", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16", seed=1003),
+    "lact_bf16_256k": LactConfig("lact_bf16_256k", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004),
+}
+
+
+def workload(name: str):
+    return WORKLOADS[name]
+
+
+def _torch_dtype(dtype: str) -> torch.dtype:
+    if dtype == "bf16":
+        return torch.bfloat16
+    if dtype == "f32":
+        return torch.float32
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _draw(gen: torch.Generator, shape, var: float, dtype: torch.dtype) -> torch.Tensor:
+    t = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    t.mul_(math.sqrt(var))
+    return t.to(dtype)
+
+
+def inplace_inputs(cfg: InplaceConfig, seed: int | None = None) -> dict:
+    """Draw the In-Place TTT layer inputs on the CPU.
+
+    Returns a dict of CPU torch tensors in the workload's dtype:
+      H, X0 [B, n, d]; W_gate, W_up [f, d]; W_down0 [d, f];
+      W_target [d, d] (indexed [d_in, d_out]); conv_w [d, K].
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(cfg.seed if seed is None else seed)
+    dt = _torch_dtype(cfg.dtype)
+    B, n, d, f, K = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.conv_k
+    out = {}
+    out["H"] = _draw(gen, (B, n, d), cfg.var_h, dt)
+    out["X0"] = _draw(gen, (B, n, d), cfg.var_x0, dt)
+    out["W_gate"] = _draw(gen, (f, d), cfg.var_gate if cfg.var_gate is not None else 1.0 / d, dt)
+    out["W_up"] = _draw(gen, (f, d), cfg.var_up if cfg.var_up is not None else 1.0 / d, dt)
+    out["W_down0"] = _draw(gen, (d, f), cfg.var_down if cfg.var_down is not None else 1.0 / f, dt)
+    out["W_target"] = _draw(gen, (d, d), cfg.var_target if cfg.var_target is not None else 1.0 / d, dt)
+    out["conv_w"] = _draw(gen, (d, K), cfg.var_conv, dt)
+    return out
+
+
+def lact_inputs(cfg: LactConfig, seed: int | None = None) -> dict:
+    """Draw the LaCT layer inputs on the CPU.
+
+    Returns q, k, v [B, H, n, dh] (L2-normalised over dh per token, then
+    rounded), W1, W3 [H, m, dh], W2 [H, dh, m].
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(cfg.seed if seed is None else seed)
+    dt = _torch_dtype(cfg.dtype)
+    B, Hh, n, dh, m = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.hidden
+    out = {}
+    for name in ("q", "k", "v"):
+        t = torch.randn(B, Hh, n, dh, generator=gen, dtype=torch.float32)
+        t = t / t.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+        out[name] = t.to(dt)
+    out["W1"] = _draw(gen, (Hh, m, dh), cfg.var_w1 if cfg.var_w1 is not None else 1.0 / dh, dt)
+    out["W3"] = _draw(gen, (Hh, m, dh), cfg.var_w3 if cfg.var_w3 is not None else 1.0 / dh, dt)
+    out["W2"] = _draw(gen, (Hh, dh, m), cfg.var_w2 if cfg.var_w2 is not None else 1.0 / m, dt)
+    return out
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of a CPU tensor (bf16 or fp32) to a float64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def bf16_round(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to the nearest bf16 (ties to even), returned as float64.
+
+    Goes through torch's float32 -> bfloat16 conversion; the float64 -> float32
+    step is exact for the values this is used on (already-representable or
+    test-constructed inputs)."""
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
