@@ -1,0 +1,249 @@
+"""Throughput of the chunk-wise TTT fast-weight layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one whole layer call on one batch of synthetic input (the seeded
+generators of ttt_inputs), inputs resident in HBM before the timed region:
+  In-Place (dot):  produce Z, produce V^ (conv + projection), fused chunk
+                   update + prefix scan, apply -- the four launches that
+                   ttt_chunk_apply_update makes, called through the C ABI's
+                   step entry points so that each kernel is bracketed by HIP
+                   events on the launch stream;
+  In-Place (mse):  ttt_chunk_apply_update (producers + in-order scan);
+  LaCT:            ttt_lact_swiglu.
+Prints one JSON line.  The CPU baseline is the float64 oracle timed on a
+bounded prefix of the same workload (whole chunks), on the host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TTT-layer tokens/s (apply+update) at 32K/128K ctx; % of bf16 MFMA peak"
+PEAK = {"bf16": 2500.0, "f32": 157.3}          # dense MFMA TFLOP/s, MI355X
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="inplace_bf16_128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the 32K-context secondary figure")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_flops(cfg):
+    """Algorithmic flops of each launch of the dot-mode step (per call)."""
+    T, d, f, K = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.conv_k
+    return {
+        "produce_z": 4.0 * T * d * f,
+        "produce_vhat": 2.0 * T * d * d + 2.0 * K * T * d,
+        "update_scan": 2.0 * T * d * f,
+        "apply": 2.0 * T * d * f,
+    }
+
+
+def kernel_bytes(cfg, esz=2):
+    """Algorithmic HBM bytes of each launch: each operand read once, each result written once."""
+    T, d, f, k, B = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.n_chunks, cfg.batch
+    return {
+        "produce_z": esz * (T * d + 2 * f * d + T * f),
+        "produce_vhat": esz * (T * d + d * d + d * cfg.conv_k + T * d),
+        "update_scan": esz * (T * f + T * d + d * f + B * k * d * f) + 4 * B * d * f,
+        "apply": esz * (T * f + B * k * d * f + T * d),
+    }
+
+
+def bench_inplace_dot(cfg, steps, warmup):
+    import torch
+
+    import chunk_wise_weight_amd as cw
+    import ttt_inputs as ti
+
+    x = ti.inplace_inputs(cfg)
+    g = {k: v.cuda() for k, v in x.items()}
+    B, n, d, f, C = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.chunk
+    k = n // C
+    dt = g["H"].dtype
+    Z = torch.empty(B, n, f, dtype=dt, device="cuda")
+    V = torch.empty(B, n, d, dtype=dt, device="cuda")
+    Wc = torch.empty(B, k, d, f, dtype=dt, device="cuda")
+    Wf = torch.empty(B, d, f, dtype=torch.float32, device="cuda")
+    O = torch.empty(B, n, d, dtype=dt, device="cuda")
+    names = ["produce_z", "produce_vhat", "update_scan", "apply"]
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"], Z)
+        if ev: ev[1].record()
+        cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"], V)
+        if ev: ev[2].record()
+        cw.ttt_chunk_update_scan(Z, V, g["W_down0"], C, cfg.eta, Wc, Wf)
+        if ev: ev[3].record()
+        cw.ttt_chunk_apply(Z, Wc, C, O)
+        if ev: ev[4].record()
+
+    for _ in range(warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {nm: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)) / steps
+           for j, nm in enumerate(names)}
+    del Z, V, Wc, O, g
+    return wall, per, Wf
+
+
+def bench_generic(cfg, steps, warmup):
+    """Whole-call timing (MSE In-Place or LaCT)."""
+    import torch
+
+    import chunk_wise_weight_amd as cw
+    import ttt_inputs as ti
+
+    if isinstance(cfg, ti.LactConfig):
+        x = ti.lact_inputs(cfg)
+        g = {k: v.cuda() for k, v in x.items()}
+        call = lambda: cw.ttt_lact_swiglu(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta,
+                                          cfg.order)
+    else:
+        x = ti.inplace_inputs(cfg)
+        g = {k: v.cuda() for k, v in x.items()}
+        call = lambda: cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"],
+                                                 g["W_target"], g["conv_w"], cfg.chunk, cfg.eta, cfg.mode)
+    for _ in range(warmup):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, {"layer": e0.elapsed_time(e1) / steps}
+
+
+def cpu_baseline(cfg, target_s):
+    """The float64 oracle on whole leading chunks of the same workload."""
+    import numpy as np
+    import threadpoolctl
+
+    import ttt_inputs as ti
+    from oracle import inplace as orc
+    from oracle import lact as olact
+
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    if isinstance(cfg, ti.LactConfig):
+        x = ti.lact_inputs(cfg)
+        run = lambda kc: olact.lact_layer(*(ti.to_f64(x[k][:, :1, : kc * cfg.chunk]) if k in "qkv"
+                                            else ti.to_f64(x[k][:1]) for k in ("q", "k", "v", "W1", "W3", "W2")),
+                                          cfg.chunk, cfg.eta, cfg.order)
+        per_tok_heads = 1
+    else:
+        x = ti.inplace_inputs(cfg)
+        ws = {k: ti.to_f64(x[k]) for k in ("W_gate", "W_up", "W_down0", "W_target", "conv_w")}
+        run = lambda kc: orc.inplace_layer(ti.to_f64(x["H"][:1, : kc * cfg.chunk]),
+                                           ti.to_f64(x["X0"][:1, : kc * cfg.chunk]), ws["W_gate"], ws["W_up"],
+                                           ws["W_down0"], ws["W_target"], ws["conv_w"], cfg.chunk, cfg.eta,
+                                           "dot" if cfg.mode == "dot_scan" else cfg.mode)
+    t0 = time.perf_counter()
+    run(1)
+    t1 = time.perf_counter() - t0
+    kc = int(max(1, min(cfg.n_chunks, target_s // max(t1, 1e-9))))
+    if kc > 1:
+        t0 = time.perf_counter()
+        run(kc)
+        t1 = time.perf_counter() - t0
+    tokens = kc * cfg.chunk
+    if isinstance(cfg, ti.LactConfig):
+        sample = f"first {kc} chunk(s) of {cfg.chunk} tokens, batch row 0, head 0 of {cfg.heads}"
+        value = tokens / t1 / cfg.heads          # whole-layer tokens/s (all heads)
+    else:
+        sample = f"first {kc} chunk(s) of {cfg.chunk} tokens of batch row 0 (of {cfg.n_chunks} x {cfg.batch})"
+        value = tokens / t1
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle", "sample": sample,
+            "seconds": t1}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+
+    import ttt_inputs as ti
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = ti.workload(args.workload)
+    dtype = cfg.dtype
+    out = {"metric": METRIC, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+           "data": "synthetic (seeded Gaussian inputs and random-init weights of the stated shapes)"}
+    if isinstance(cfg, ti.LactConfig):
+        out["config"] = {"workload": cfg.name, "batch": cfg.batch, "heads": cfg.heads, "seq_len": cfg.seq_len,
+                         "head_dim": cfg.head_dim, "hidden": cfg.hidden, "chunk": cfg.chunk, "eta": cfg.eta,
+                         "order": cfg.order}
+    else:
+        out["config"] = {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_len, "d_model": cfg.d_model,
+                         "d_ff": cfg.d_ff, "chunk": cfg.chunk, "conv_k": cfg.conv_k, "eta": cfg.eta,
+                         "mode": cfg.mode}
+
+    if not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot":
+        wall, per, _ = bench_inplace_dot(cfg, args.steps, args.warmup)
+        fl, by = kernel_flops(cfg), kernel_bytes(cfg, 2 if dtype == "bf16" else 4)
+        kern = {}
+        for nm, ms in per.items():
+            tf = fl[nm] / (ms * 1e-3) / 1e12
+            kern[nm] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac_mfma_peak": round(tf / PEAK[dtype], 4),
+                        "alg_GBs": round(by[nm] / (ms * 1e-3) / 1e9, 1)}
+        out["kernels"] = kern
+        dom = max(per, key=per.get)
+        ach = fl[dom] / (per[dom] * 1e-3) / 1e12
+        out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK[dtype],
+                           "unit": "TFLOP/s", "frac": round(ach / PEAK[dtype], 4), "traffic": None}
+    else:
+        wall, per = bench_generic(cfg, args.steps, args.warmup)
+        ms = per["layer"]
+        ach = cfg.flops() / (ms * 1e-3) / 1e12
+        out["roofline"] = {"kernel": "layer", "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK[dtype],
+                           "unit": "TFLOP/s", "frac": round(ach / PEAK[dtype], 4), "traffic": None}
+    ms_step = wall / args.steps * 1e3
+    out["ms_per_step"] = round(ms_step, 4)
+    out["value"] = round(cfg.tokens / (ms_step * 1e-3), 1)
+    tf = cfg.flops() / (ms_step * 1e-3) / 1e12
+    out["tflops"] = round(tf, 1)
+    out["frac_bf16_mfma_peak"] = round(tf / PEAK["bf16"], 4)
+    if args.workload == "inplace_bf16_128k" and not args.no_secondary:
+        c2 = ti.workload("inplace_bf16_32k")
+        w2, p2, _ = bench_inplace_dot(c2, max(5, args.steps // 2), args.warmup)
+        ms2 = w2 / max(5, args.steps // 2) * 1e3
+        out["secondary"] = {"workload": c2.name, "ms_per_step": round(ms2, 4),
+                            "value": round(c2.tokens / (ms2 * 1e-3), 1),
+                            "tflops": round(c2.flops() / (ms2 * 1e-3) / 1e12, 1),
+                            "frac_bf16_mfma_peak": round(c2.flops() / (ms2 * 1e-3) / 1e12 / PEAK["bf16"], 4)}
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

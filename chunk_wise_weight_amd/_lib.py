@@ -1,0 +1,327 @@
+"""ctypes marshalling for libttt.so.  No arithmetic of the layer happens here:
+the functions check that the tensors they are given match the shape they
+declare (the C ABI sees only raw pointers), allocate outputs and workspace
+with torch on the tensors' device, and pass pointers and the current stream."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libttt.so")
+
+TTT_OK, TTT_ERR_ARG, TTT_ERR_SHAPE, TTT_ERR_DTYPE, TTT_ERR_WORKSPACE, TTT_ERR_DEVICE, TTT_ERR_UNSUPPORTED = range(7)
+TTT_F32, TTT_BF16 = 0, 1
+TTT_MODE_DOT, TTT_MODE_MSE, TTT_MODE_DOT_SCAN = 0, 1, 2
+TTT_UPDATE_THEN_APPLY, TTT_APPLY_THEN_UPDATE = 0, 1
+
+_MODES = {"dot": TTT_MODE_DOT, "mse": TTT_MODE_MSE, "dot_scan": TTT_MODE_DOT_SCAN}
+_ORDERS = {"update_then_apply": TTT_UPDATE_THEN_APPLY, "apply_then_update": TTT_APPLY_THEN_UPDATE}
+_DTYPES = {torch.float32: TTT_F32, torch.bfloat16: TTT_BF16}
+
+
+class InplaceShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("batch", "seq_len", "d_model", "d_ff", "chunk", "conv_k")]
+
+
+class LactShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("batch", "heads", "seq_len", "head_dim", "hidden", "chunk")]
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_S = ctypes.c_size_t
+_SIGNATURES = {
+    "ttt_status_string": (ctypes.c_char_p, [_I]),
+    "ttt_inplace_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _I, ctypes.POINTER(_S)]),
+    "ttt_chunk_apply_update": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _S, _P]),
+    "ttt_core_apply_update": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "ttt_produce_z": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P]),
+    "ttt_produce_vhat": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P]),
+    "ttt_chunk_delta": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P]),
+    "ttt_chunk_scan": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P]),
+    "ttt_chunk_update_scan": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P]),
+    "ttt_chunk_apply": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P]),
+    "ttt_lact_workspace_bytes": (_I, [ctypes.POINTER(LactShape), _I, ctypes.POINTER(_S)]),
+    "ttt_lact_swiglu": (_I, [ctypes.POINTER(LactShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                             _S, _P]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libttt.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is missing: build it with `python -m chunk_wise_weight_amd.build`")
+        handle = ctypes.CDLL(lib_path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGNATURES)
+
+
+def status_string(status: int) -> str:
+    return lib().ttt_status_string(int(status)).decode()
+
+
+def _check(status: int, what: str):
+    if status != TTT_OK:
+        raise TTTError(status, what)
+
+
+def _dt(dtype: torch.dtype) -> int:
+    if dtype not in _DTYPES:
+        raise TypeError(f"dtype must be float32 or bfloat16, got {dtype}")
+    return _DTYPES[dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (the layer runs only in the HIP library)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _mode(mode) -> int:
+    if isinstance(mode, str):
+        return _MODES[mode]
+    return int(mode)
+
+
+def _inplace_shape(B, n, d, f, chunk, K) -> InplaceShape:
+    return InplaceShape(int(B), int(n), int(d), int(f), int(chunk), int(K))
+
+
+def ttt_inplace_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, mode="dot", with_producers=True) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().ttt_inplace_workspace_bytes(ctypes.byref(shape), _dt(dtype), _mode(mode), int(bool(with_producers)),
+                                             ctypes.byref(out)), "ttt_inplace_workspace_bytes")
+    return out.value
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is not None:
+        if workspace.device.type != "cuda" or workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk: int, eta: float, mode="dot",
+                           O=None, W_final=None, workspace=None):
+    """The whole In-Place layer.  Returns (O [B, n, d], W_final [B, d, f] fp32)."""
+    B, n, d = H.shape
+    f = W_gate.shape[0]
+    K = conv_w.shape[1]
+    dt, dev = H.dtype, H.device
+    for name, t, shp in (("H", H, (B, n, d)), ("X0", X0, (B, n, d)), ("W_gate", W_gate, (f, d)),
+                         ("W_up", W_up, (f, d)), ("W_down0", W_down0, (d, f)), ("W_target", W_target, (d, d)),
+                         ("conv_w", conv_w, (d, K))):
+        _need(t, name, shp, dt, dev)
+    shape = _inplace_shape(B, n, d, f, chunk, K)
+    O = torch.empty(B, n, d, dtype=dt, device=dev) if O is None else O
+    W_final = torch.empty(B, d, f, dtype=torch.float32, device=dev) if W_final is None else W_final
+    _need(O, "O", (B, n, d), dt, dev)
+    _need(W_final, "W_final", (B, d, f), torch.float32, dev)
+    nbytes = ttt_inplace_workspace_bytes(shape, dt, mode, True)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib().ttt_chunk_apply_update(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H), _ptr(X0),
+                                        _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target), _ptr(conv_w),
+                                        _ptr(O), _ptr(W_final), _ptr(ws), nbytes, _stream(dev)),
+           "ttt_chunk_apply_update")
+    return O, W_final
+
+
+def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", O=None, W_final=None,
+                          workspace=None):
+    """The chunk loop given Z [B, n, f] and Vhat [B, n, d].  Returns (O, W_final)."""
+    B, n, f = Z.shape
+    d = Vhat.shape[2]
+    dt, dev = Z.dtype, Z.device
+    _need(Z, "Z", (B, n, f), dt, dev)
+    _need(Vhat, "Vhat", (B, n, d), dt, dev)
+    _need(W_down0, "W_down0", (d, f), dt, dev)
+    shape = _inplace_shape(B, n, d, f, chunk, 1)
+    O = torch.empty(B, n, d, dtype=dt, device=dev) if O is None else O
+    W_final = torch.empty(B, d, f, dtype=torch.float32, device=dev) if W_final is None else W_final
+    _need(O, "O", (B, n, d), dt, dev)
+    _need(W_final, "W_final", (B, d, f), torch.float32, dev)
+    nbytes = ttt_inplace_workspace_bytes(shape, dt, mode, False)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib().ttt_core_apply_update(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(Z), _ptr(Vhat),
+                                       _ptr(W_down0), _ptr(O), _ptr(W_final), _ptr(ws), nbytes, _stream(dev)),
+           "ttt_core_apply_update")
+    return O, W_final
+
+
+def ttt_produce_z(H, W_gate, W_up, Z=None):
+    """Z [B, n, f] = silu(H W_gate^T) * (H W_up^T)."""
+    B, n, d = H.shape
+    f = W_gate.shape[0]
+    dt, dev = H.dtype, H.device
+    _need(H, "H", (B, n, d), dt, dev)
+    _need(W_gate, "W_gate", (f, d), dt, dev)
+    _need(W_up, "W_up", (f, d), dt, dev)
+    Z = torch.empty(B, n, f, dtype=dt, device=dev) if Z is None else Z
+    _need(Z, "Z", (B, n, f), dt, dev)
+    shape = _inplace_shape(B, n, d, f, max(n, 8), 1)
+    _check(lib().ttt_produce_z(ctypes.byref(shape), _dt(dt), _ptr(H), _ptr(W_gate), _ptr(W_up), _ptr(Z),
+                               _stream(dev)), "ttt_produce_z")
+    return Z
+
+
+def ttt_produce_vhat(X0, conv_w, W_target, Vhat=None):
+    """Vhat [B, n, d] = CausalDepthwiseConv1D(X0) W_target."""
+    B, n, d = X0.shape
+    K = conv_w.shape[1]
+    dt, dev = X0.dtype, X0.device
+    _need(X0, "X0", (B, n, d), dt, dev)
+    _need(conv_w, "conv_w", (d, K), dt, dev)
+    _need(W_target, "W_target", (d, d), dt, dev)
+    Vhat = torch.empty(B, n, d, dtype=dt, device=dev) if Vhat is None else Vhat
+    _need(Vhat, "Vhat", (B, n, d), dt, dev)
+    shape = _inplace_shape(B, n, d, 8, max(n, 8), K)
+    _check(lib().ttt_produce_vhat(ctypes.byref(shape), _dt(dt), _ptr(X0), _ptr(conv_w), _ptr(W_target), _ptr(Vhat),
+                                  _stream(dev)), "ttt_produce_vhat")
+    return Vhat
+
+
+def ttt_chunk_delta(Z, Vhat, chunk: int, dW=None):
+    """dW [B, k, d, f] fp32, dW[b, c] = Vhat_c^T Z_c."""
+    B, n, f = Z.shape
+    d = Vhat.shape[2]
+    dt, dev = Z.dtype, Z.device
+    _need(Z, "Z", (B, n, f), dt, dev)
+    _need(Vhat, "Vhat", (B, n, d), dt, dev)
+    k = n // chunk if chunk > 0 else 0
+    dW = torch.empty(B, k, d, f, dtype=torch.float32, device=dev) if dW is None else dW
+    _need(dW, "dW", (B, k, d, f), torch.float32, dev)
+    shape = _inplace_shape(B, n, d, f, chunk, 1)
+    _check(lib().ttt_chunk_delta(ctypes.byref(shape), _dt(dt), _ptr(Z), _ptr(Vhat), _ptr(dW), _stream(dev)),
+           "ttt_chunk_delta")
+    return dW
+
+
+def ttt_chunk_scan(dW, W_down0, eta: float, chunk: int, seq_len: int, Wc=None, W_final=None):
+    """Exclusive prefix over chunks.  Returns (Wc [B, k, d, f] dtype, W_final [B, d, f] fp32)."""
+    B, k, d, f = dW.shape
+    dt, dev = W_down0.dtype, W_down0.device
+    _need(dW, "dW", (B, k, d, f), torch.float32, dev)
+    _need(W_down0, "W_down0", (d, f), dt, dev)
+    Wc = torch.empty(B, k, d, f, dtype=dt, device=dev) if Wc is None else Wc
+    W_final = torch.empty(B, d, f, dtype=torch.float32, device=dev) if W_final is None else W_final
+    _need(Wc, "Wc", (B, k, d, f), dt, dev)
+    _need(W_final, "W_final", (B, d, f), torch.float32, dev)
+    if seq_len != k * chunk:
+        raise ValueError("seq_len must equal k * chunk")
+    shape = _inplace_shape(B, seq_len, d, f, chunk, 1)
+    _check(lib().ttt_chunk_scan(ctypes.byref(shape), _dt(dt), float(eta), _ptr(W_down0), _ptr(dW), _ptr(Wc),
+                                _ptr(W_final), _stream(dev)), "ttt_chunk_scan")
+    return Wc, W_final
+
+
+def ttt_chunk_update_scan(Z, Vhat, W_down0, chunk: int, eta: float, Wc=None, W_final=None):
+    """Fused deltas + prefix.  Returns (Wc [B, k, d, f] dtype, W_final fp32)."""
+    B, n, f = Z.shape
+    d = Vhat.shape[2]
+    dt, dev = Z.dtype, Z.device
+    _need(Z, "Z", (B, n, f), dt, dev)
+    _need(Vhat, "Vhat", (B, n, d), dt, dev)
+    _need(W_down0, "W_down0", (d, f), dt, dev)
+    k = n // chunk if chunk > 0 else 0
+    Wc = torch.empty(B, k, d, f, dtype=dt, device=dev) if Wc is None else Wc
+    W_final = torch.empty(B, d, f, dtype=torch.float32, device=dev) if W_final is None else W_final
+    _need(Wc, "Wc", (B, k, d, f), dt, dev)
+    _need(W_final, "W_final", (B, d, f), torch.float32, dev)
+    shape = _inplace_shape(B, n, d, f, chunk, 1)
+    _check(lib().ttt_chunk_update_scan(ctypes.byref(shape), _dt(dt), float(eta), _ptr(W_down0), _ptr(Z), _ptr(Vhat),
+                                       _ptr(Wc), _ptr(W_final), _stream(dev)), "ttt_chunk_update_scan")
+    return Wc, W_final
+
+
+def ttt_chunk_apply(Z, Wc, chunk: int, O=None):
+    """O [B, n, d], O_c = Z_c Wc[b, c]^T."""
+    B, n, f = Z.shape
+    k, d = Wc.shape[1], Wc.shape[2]
+    dt, dev = Z.dtype, Z.device
+    _need(Z, "Z", (B, n, f), dt, dev)
+    _need(Wc, "Wc", (B, k, d, f), dt, dev)
+    if k * chunk != n:
+        raise ValueError("Wc must hold one state per chunk")
+    O = torch.empty(B, n, d, dtype=dt, device=dev) if O is None else O
+    _need(O, "O", (B, n, d), dt, dev)
+    shape = _inplace_shape(B, n, d, f, chunk, 1)
+    _check(lib().ttt_chunk_apply(ctypes.byref(shape), _dt(dt), _ptr(Z), _ptr(Wc), _ptr(O), _stream(dev)),
+           "ttt_chunk_apply")
+    return O
+
+
+def ttt_lact_workspace_bytes(shape: LactShape, dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().ttt_lact_workspace_bytes(ctypes.byref(shape), _dt(dtype), ctypes.byref(out)),
+           "ttt_lact_workspace_bytes")
+    return out.value
+
+
+def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_then_apply", O=None, finals=None,
+                    workspace=None):
+    """LaCT SwiGLU layer.  Returns (O [B, H, n, dh], W1_f, W3_f [B, H, m, dh], W2_f [B, H, dh, m])."""
+    B, Hh, n, dh = q.shape
+    m = W1.shape[1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, Hh, n, dh)), ("k", k, (B, Hh, n, dh)), ("v", v, (B, Hh, n, dh)),
+                         ("W1", W1, (Hh, m, dh)), ("W3", W3, (Hh, m, dh)), ("W2", W2, (Hh, dh, m))):
+        _need(t, name, shp, dt, dev)
+    O = torch.empty(B, Hh, n, dh, dtype=dt, device=dev) if O is None else O
+    _need(O, "O", (B, Hh, n, dh), dt, dev)
+    if finals is None:
+        finals = (torch.empty(B, Hh, m, dh, dtype=torch.float32, device=dev),
+                  torch.empty(B, Hh, m, dh, dtype=torch.float32, device=dev),
+                  torch.empty(B, Hh, dh, m, dtype=torch.float32, device=dev))
+    W1f, W3f, W2f = finals
+    _need(W1f, "W1_f", (B, Hh, m, dh), torch.float32, dev)
+    _need(W3f, "W3_f", (B, Hh, m, dh), torch.float32, dev)
+    _need(W2f, "W2_f", (B, Hh, dh, m), torch.float32, dev)
+    shape = LactShape(B, Hh, n, dh, m, int(chunk))
+    nbytes = ttt_lact_workspace_bytes(shape, dt)
+    ws = _workspace(nbytes, dev, workspace)
+    ordc = _ORDERS[order] if isinstance(order, str) else int(order)
+    _check(lib().ttt_lact_swiglu(ctypes.byref(shape), _dt(dt), ordc, float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(W1),
+                                 _ptr(W3), _ptr(W2), _ptr(O), _ptr(W1f), _ptr(W3f), _ptr(W2f), _ptr(ws), nbytes,
+                                 _stream(dev)), "ttt_lact_swiglu")
+    return O, W1f, W3f, W2f

@@ -1,0 +1,376 @@
+// C ABI of the chunk-wise TTT library: argument validation (always complete
+// before any device work), workspace planning and dispatch to the launchers.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "launch.hpp"
+#include "ttt.h"
+
+namespace {
+
+using ttt::bf16;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+
+// Steps of the bf16 / fp32 K loop: the fused update-scan needs chunk
+// boundaries on step boundaries.
+inline int64_t kstep(int dtype) { return dtype == TTT_BF16 ? 64 : 32; }
+
+struct Plan {
+  int64_t B, n, d, f, C, K, k;
+  size_t esz;
+  bool fused;
+  size_t off_Z, off_V, off_Wc, off_dW, off_R, off_Wsh, total;
+};
+
+int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
+  if (s == nullptr) return TTT_ERR_ARG;
+  if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
+  if (s->batch < 0 || s->seq_len < 0 || s->d_model <= 0 || s->d_ff <= 0 || s->chunk <= 0 || s->conv_k <= 0)
+    return TTT_ERR_SHAPE;
+  if (s->seq_len % s->chunk != 0) return TTT_ERR_SHAPE;
+  if (s->d_model % 8 || s->d_ff % 8 || s->chunk % 8 || s->conv_k > 8) return TTT_ERR_UNSUPPORTED;
+  // index and grid ranges the kernels are built for
+  const int64_t lim = (int64_t)1 << 30;
+  if (s->d_model > (1 << 16) || s->d_ff > (1 << 20) || s->seq_len > lim || s->batch > lim ||
+      s->batch * s->seq_len > lim)
+    return TTT_ERR_UNSUPPORTED;
+  const int64_t rows_tiles = (s->batch * s->seq_len + 255) / 256;
+  if (rows_tiles * ((s->d_ff + 127) / 128) > INT32_MAX) return TTT_ERR_UNSUPPORTED;
+  const int64_t k = s->seq_len / s->chunk;
+  if (s->batch * k * ((s->d_model + 255) / 256) * ((s->d_ff + 255) / 256) > INT32_MAX) return TTT_ERR_UNSUPPORTED;
+  return TTT_OK;
+}
+
+int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, Plan* p) {
+  int st = check_inplace_shape(s, dtype);
+  if (st != TTT_OK) return st;
+  if (mode != TTT_MODE_DOT && mode != TTT_MODE_MSE && mode != TTT_MODE_DOT_SCAN) return TTT_ERR_ARG;
+  p->B = s->batch;
+  p->n = s->seq_len;
+  p->d = s->d_model;
+  p->f = s->d_ff;
+  p->C = s->chunk;
+  p->K = s->conv_k;
+  p->k = s->seq_len / s->chunk;
+  p->esz = dtype == TTT_BF16 ? 2 : 4;
+  p->fused = mode == TTT_MODE_DOT && p->C % kstep(dtype) == 0;
+  const size_t BN = (size_t)p->B * p->n, DF = (size_t)p->d * p->f;
+  size_t off = 0;
+  p->off_Z = p->off_V = p->off_Wc = p->off_dW = p->off_R = p->off_Wsh = 0;
+  if (producers) {
+    p->off_Z = off;
+    off += align_up(BN * p->f * p->esz);
+    p->off_V = off;
+    off += align_up(BN * p->d * p->esz);
+  }
+  if (mode == TTT_MODE_DOT || mode == TTT_MODE_DOT_SCAN) {
+    p->off_Wc = off;
+    off += align_up((size_t)p->B * p->k * DF * p->esz);
+    if (!p->fused) {
+      p->off_dW = off;
+      off += align_up((size_t)p->B * p->k * DF * 4);
+    }
+  } else {
+    p->off_R = off;
+    off += align_up((size_t)p->B * p->C * p->d * p->esz);
+    if (dtype == TTT_BF16) {
+      p->off_Wsh = off;
+      off += align_up((size_t)p->B * DF * p->esz);
+    }
+  }
+  p->total = off;
+  return TTT_OK;
+}
+
+inline int dev(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE; }
+
+// W_final[b] = W_down0 for every row (no chunks): the scan with zero chunks.
+template <typename T>
+int fill_initial_state(const Plan& p, const void* W0, float* Wf, hipStream_t s) {
+  return dev(ttt::launch_chunk_scan<T>(nullptr, (const T*)W0, nullptr, Wf, (int)p.B, 0, (int64_t)p.d * p.f, 0.f, s));
+}
+
+template <typename T>
+int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Vv, const void* W0v, void* Ov,
+             float* Wf, char* ws, hipStream_t s) {
+  const T* Z = (const T*)Zv;
+  const T* V = (const T*)Vv;
+  const T* W0 = (const T*)W0v;
+  T* O = (T*)Ov;
+  const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
+  const int64_t df = (int64_t)d * f;
+  if (p.B == 0) return TTT_OK;
+  if (p.n == 0) return fill_initial_state<T>(p, W0v, Wf, s);
+  if (mode == TTT_MODE_MSE) {
+    T* R = (T*)(ws + p.off_R);
+    T* Wsh = p.esz == 2 ? (T*)(ws + p.off_Wsh) : nullptr;
+    const T* Wcur = p.esz == 2 ? (const T*)Wsh : (const T*)(const void*)Wf;
+    for (int c = 0; c < k; ++c) {
+      int st = dev(ttt::launch_mse_chunk<T>(Z, V, W0, Wcur, Wf, Wsh, O, R, B, n, d, f, C, c, eta, s));
+      if (st != TTT_OK) return st;
+    }
+    return TTT_OK;
+  }
+  T* Wc = (T*)(ws + p.off_Wc);
+  int st;
+  if (p.fused) {
+    st = dev(ttt::launch_chunk_update_scan<T>(Z, V, W0, Wc, Wf, B, n, d, f, C, eta, s));
+  } else {
+    float* dW = (float*)(ws + p.off_dW);
+    st = dev(ttt::launch_chunk_delta<T>(Z, V, dW, B, n, d, f, C, s));
+    if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, df, eta, s));
+  }
+  if (st != TTT_OK) return st;
+  return dev(ttt::launch_apply<T>(Z, Wc, (int64_t)k * df, df, O, B, n, d, f, C, s));
+}
+
+int check_ws(const Plan& p, void* ws, size_t bytes) {
+  if (p.total == 0) return TTT_OK;
+  if (ws == nullptr || !aligned16(ws) || bytes < p.total) return TTT_ERR_WORKSPACE;
+  return TTT_OK;
+}
+
+inline bool finite(float x) { return isfinite(x); }
+
+}  // namespace
+
+extern "C" {
+
+const char* ttt_status_string(int status) {
+  switch (status) {
+    case TTT_OK: return "TTT_OK";
+    case TTT_ERR_ARG: return "TTT_ERR_ARG: null or misaligned pointer, unknown mode/order, or non-finite eta";
+    case TTT_ERR_SHAPE: return "TTT_ERR_SHAPE: negative or zero size, or seq_len not a multiple of chunk";
+    case TTT_ERR_DTYPE: return "TTT_ERR_DTYPE: dtype must be TTT_F32 or TTT_BF16";
+    case TTT_ERR_WORKSPACE: return "TTT_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case TTT_ERR_DEVICE: return "TTT_ERR_DEVICE: the HIP runtime rejected a launch";
+    case TTT_ERR_UNSUPPORTED: return "TTT_ERR_UNSUPPORTED: sizes outside what this build handles";
+    default: return "unknown status";
+  }
+}
+
+int ttt_inplace_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int mode, int with_producers,
+                                size_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_ARG;
+  Plan p;
+  int st = make_plan(shape, dtype, mode, with_producers != 0, &p);
+  if (st != TTT_OK) return st;
+  *bytes = p.total;
+  return TTT_OK;
+}
+
+int ttt_chunk_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* H,
+                           const void* X0, const void* W_gate, const void* W_up, const void* W_down0,
+                           const void* W_target, const void* conv_w, void* O, float* W_final, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, dtype, mode, true, &p);
+  if (st != TTT_OK) return st;
+  if (!finite(eta)) return TTT_ERR_ARG;
+  if (p.B > 0) {
+    if (!ok_ptr(W_down0) || !ok_ptr(W_final)) return TTT_ERR_ARG;
+    if (p.n > 0 && (!ok_ptr(H) || !ok_ptr(X0) || !ok_ptr(W_gate) || !ok_ptr(W_up) || !ok_ptr(W_target) ||
+                    !ok_ptr(conv_w) || !ok_ptr(O)))
+      return TTT_ERR_ARG;
+  }
+  if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int64_t rows = p.B * p.n;
+  if (rows > 0) {
+    if (dtype == TTT_BF16) {
+      st = dev(ttt::launch_produce_z<bf16>((const bf16*)H, (const bf16*)W_gate, (const bf16*)W_up,
+                                           (bf16*)(ws + p.off_Z), rows, (int)p.d, (int)p.f, s));
+      if (st == TTT_OK)
+        st = dev(ttt::launch_produce_vhat<bf16>((const bf16*)X0, (const bf16*)conv_w, (const bf16*)W_target,
+                                                (bf16*)(ws + p.off_V), rows, (int)p.n, (int)p.d, (int)p.K, s));
+    } else {
+      st = dev(ttt::launch_produce_z<float>((const float*)H, (const float*)W_gate, (const float*)W_up,
+                                            (float*)(ws + p.off_Z), rows, (int)p.d, (int)p.f, s));
+      if (st == TTT_OK)
+        st = dev(ttt::launch_produce_vhat<float>((const float*)X0, (const float*)conv_w, (const float*)W_target,
+                                                 (float*)(ws + p.off_V), rows, (int)p.n, (int)p.d, (int)p.K, s));
+    }
+    if (st != TTT_OK) return st;
+  }
+  if (dtype == TTT_BF16)
+    return run_core<bf16>(p, mode, eta, ws + p.off_Z, ws + p.off_V, W_down0, O, W_final, ws, s);
+  return run_core<float>(p, mode, eta, ws + p.off_Z, ws + p.off_V, W_down0, O, W_final, ws, s);
+}
+
+int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* Z,
+                          const void* Vhat, const void* W_down0, void* O, float* W_final, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, dtype, mode, false, &p);
+  if (st != TTT_OK) return st;
+  if (!finite(eta)) return TTT_ERR_ARG;
+  if (p.B > 0) {
+    if (!ok_ptr(W_down0) || !ok_ptr(W_final)) return TTT_ERR_ARG;
+    if (p.n > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(O))) return TTT_ERR_ARG;
+  }
+  if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == TTT_BF16) return run_core<bf16>(p, mode, eta, Z, Vhat, W_down0, O, W_final, (char*)workspace, s);
+  return run_core<float>(p, mode, eta, Z, Vhat, W_down0, O, W_final, (char*)workspace, s);
+}
+
+int ttt_produce_z(const ttt_inplace_shape* shape, int dtype, const void* H, const void* W_gate, const void* W_up,
+                  void* Z, void* stream) {
+  int st = check_inplace_shape(shape, dtype);
+  if (st != TTT_OK) return st;
+  const int64_t rows = shape->batch * shape->seq_len;
+  if (rows == 0) return TTT_OK;
+  if (!ok_ptr(H) || !ok_ptr(W_gate) || !ok_ptr(W_up) || !ok_ptr(Z)) return TTT_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int d = (int)shape->d_model, f = (int)shape->d_ff;
+  if (dtype == TTT_BF16)
+    return dev(ttt::launch_produce_z<bf16>((const bf16*)H, (const bf16*)W_gate, (const bf16*)W_up, (bf16*)Z, rows, d,
+                                           f, s));
+  return dev(ttt::launch_produce_z<float>((const float*)H, (const float*)W_gate, (const float*)W_up, (float*)Z, rows,
+                                          d, f, s));
+}
+
+int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, const void* X0, const void* conv_w,
+                     const void* W_target, void* Vhat, void* stream) {
+  int st = check_inplace_shape(shape, dtype);
+  if (st != TTT_OK) return st;
+  const int64_t rows = shape->batch * shape->seq_len;
+  if (rows == 0) return TTT_OK;
+  if (!ok_ptr(X0) || !ok_ptr(conv_w) || !ok_ptr(W_target) || !ok_ptr(Vhat)) return TTT_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int n = (int)shape->seq_len, d = (int)shape->d_model, K = (int)shape->conv_k;
+  if (dtype == TTT_BF16)
+    return dev(ttt::launch_produce_vhat<bf16>((const bf16*)X0, (const bf16*)conv_w, (const bf16*)W_target,
+                                              (bf16*)Vhat, rows, n, d, K, s));
+  return dev(ttt::launch_produce_vhat<float>((const float*)X0, (const float*)conv_w, (const float*)W_target,
+                                             (float*)Vhat, rows, n, d, K, s));
+}
+
+int ttt_chunk_delta(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Vhat, float* dW,
+                    void* stream) {
+  int st = check_inplace_shape(shape, dtype);
+  if (st != TTT_OK) return st;
+  if (shape->batch * shape->seq_len == 0) return TTT_OK;
+  if (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(dW)) return TTT_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int B = (int)shape->batch, n = (int)shape->seq_len, d = (int)shape->d_model, f = (int)shape->d_ff,
+            C = (int)shape->chunk;
+  if (dtype == TTT_BF16)
+    return dev(ttt::launch_chunk_delta<bf16>((const bf16*)Z, (const bf16*)Vhat, dW, B, n, d, f, C, s));
+  return dev(ttt::launch_chunk_delta<float>((const float*)Z, (const float*)Vhat, dW, B, n, d, f, C, s));
+}
+
+int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const void* W_down0, const float* dW,
+                   void* Wc, float* W_final, void* stream) {
+  int st = check_inplace_shape(shape, dtype);
+  if (st != TTT_OK) return st;
+  if (!finite(eta)) return TTT_ERR_ARG;
+  if (shape->batch == 0) return TTT_OK;
+  const int k = (int)(shape->seq_len / shape->chunk);
+  if (!ok_ptr(W_down0) || !ok_ptr(W_final)) return TTT_ERR_ARG;
+  if (k > 0 && (!ok_ptr(dW) || !ok_ptr(Wc))) return TTT_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t df = shape->d_model * shape->d_ff;
+  if (dtype == TTT_BF16)
+    return dev(ttt::launch_chunk_scan<bf16>(dW, (const bf16*)W_down0, (bf16*)Wc, W_final, (int)shape->batch, k, df,
+                                            eta, s));
+  return dev(ttt::launch_chunk_scan<float>(dW, (const float*)W_down0, (float*)Wc, W_final, (int)shape->batch, k, df,
+                                           eta, s));
+}
+
+int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, float eta, const void* W_down0, const void* Z,
+                          const void* Vhat, void* Wc, float* W_final, void* stream) {
+  int st = check_inplace_shape(shape, dtype);
+  if (st != TTT_OK) return st;
+  if (!finite(eta)) return TTT_ERR_ARG;
+  if (shape->chunk % kstep(dtype) != 0) return TTT_ERR_UNSUPPORTED;
+  if (shape->batch == 0) return TTT_OK;
+  if (!ok_ptr(W_down0) || !ok_ptr(W_final)) return TTT_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int B = (int)shape->batch, n = (int)shape->seq_len, d = (int)shape->d_model, f = (int)shape->d_ff,
+            C = (int)shape->chunk;
+  const int64_t df = (int64_t)d * f;
+  if (n == 0) {
+    if (dtype == TTT_BF16)
+      return dev(ttt::launch_chunk_scan<bf16>(nullptr, (const bf16*)W_down0, nullptr, W_final, B, 0, df, 0.f, s));
+    return dev(ttt::launch_chunk_scan<float>(nullptr, (const float*)W_down0, nullptr, W_final, B, 0, df, 0.f, s));
+  }
+  if (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(Wc)) return TTT_ERR_ARG;
+  if (dtype == TTT_BF16)
+    return dev(ttt::launch_chunk_update_scan<bf16>((const bf16*)Z, (const bf16*)Vhat, (const bf16*)W_down0, (bf16*)Wc,
+                                                   W_final, B, n, d, f, C, eta, s));
+  return dev(ttt::launch_chunk_update_scan<float>((const float*)Z, (const float*)Vhat, (const float*)W_down0,
+                                                  (float*)Wc, W_final, B, n, d, f, C, eta, s));
+}
+
+int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Wc, void* O, void* stream) {
+  int st = check_inplace_shape(shape, dtype);
+  if (st != TTT_OK) return st;
+  if (shape->batch * shape->seq_len == 0) return TTT_OK;
+  if (!ok_ptr(Z) || !ok_ptr(Wc) || !ok_ptr(O)) return TTT_ERR_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int B = (int)shape->batch, n = (int)shape->seq_len, d = (int)shape->d_model, f = (int)shape->d_ff,
+            C = (int)shape->chunk;
+  const int64_t df = (int64_t)d * f, k = n / C;
+  if (dtype == TTT_BF16)
+    return dev(ttt::launch_apply<bf16>((const bf16*)Z, (const bf16*)Wc, k * df, df, (bf16*)O, B, n, d, f, C, s));
+  return dev(ttt::launch_apply<float>((const float*)Z, (const float*)Wc, k * df, df, (float*)O, B, n, d, f, C, s));
+}
+
+// ------------------------------------------------------------------ LaCT
+
+static int check_lact(const ttt_lact_shape* s, int dtype) {
+  if (s == nullptr) return TTT_ERR_ARG;
+  if (dtype != TTT_F32 && dtype != TTT_BF16) return TTT_ERR_DTYPE;
+  if (s->batch < 0 || s->heads <= 0 || s->seq_len < 0 || s->head_dim <= 0 || s->hidden <= 0 || s->chunk <= 0)
+    return TTT_ERR_SHAPE;
+  if (s->seq_len % s->chunk != 0) return TTT_ERR_SHAPE;
+  if (s->head_dim % 8 || s->hidden % 8 || s->chunk % 8) return TTT_ERR_UNSUPPORTED;
+  const int64_t lim = (int64_t)1 << 30;
+  if (s->head_dim > 8192 || s->hidden > 65536 || s->seq_len > lim || s->batch * s->heads > 65536 ||
+      s->batch * s->heads * s->seq_len > lim)
+    return TTT_ERR_UNSUPPORTED;
+  return TTT_OK;
+}
+
+int ttt_lact_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_ARG;
+  int st = check_lact(shape, dtype);
+  if (st != TTT_OK) return st;
+  const int B = (int)shape->batch, H = (int)shape->heads, n = (int)shape->seq_len, dh = (int)shape->head_dim,
+            m = (int)shape->hidden, C = (int)shape->chunk;
+  *bytes = dtype == TTT_BF16 ? ttt::lact_workspace_bytes<bf16>(B, H, n, dh, m, C)
+                             : ttt::lact_workspace_bytes<float>(B, H, n, dh, m, C);
+  return TTT_OK;
+}
+
+int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta, const void* q, const void* k,
+                    const void* v, const void* W1, const void* W3, const void* W2, void* O, float* W1_f, float* W3_f,
+                    float* W2_f, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_lact(shape, dtype);
+  if (st != TTT_OK) return st;
+  if (order != TTT_UPDATE_THEN_APPLY && order != TTT_APPLY_THEN_UPDATE) return TTT_ERR_ARG;
+  if (!finite(eta)) return TTT_ERR_ARG;
+  const int B = (int)shape->batch, H = (int)shape->heads, n = (int)shape->seq_len, dh = (int)shape->head_dim,
+            m = (int)shape->hidden, C = (int)shape->chunk;
+  if (B == 0) return TTT_OK;
+  if (!ok_ptr(W1) || !ok_ptr(W3) || !ok_ptr(W2) || !ok_ptr(W1_f) || !ok_ptr(W3_f) || !ok_ptr(W2_f))
+    return TTT_ERR_ARG;
+  if (n > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(O))) return TTT_ERR_ARG;
+  const size_t need = dtype == TTT_BF16 ? ttt::lact_workspace_bytes<bf16>(B, H, n, dh, m, C)
+                                        : ttt::lact_workspace_bytes<float>(B, H, n, dh, m, C);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)) return TTT_ERR_WORKSPACE;
+  ttt::LactArgs a{B, H, n, dh, m, C, order, eta, q, k, v, W1, W3, W2, O, W1_f, W3_f, W2_f, (char*)workspace};
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == TTT_BF16 ? ttt::launch_lact<bf16>(a, s) : ttt::launch_lact<float>(a, s);
+  if (e == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;
+  return dev(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Shared device types and helpers for the gfx950 (CDNA4) kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+// Elements of T per 16-byte chunk (the unit of every global and LDS access).
+template <typename T> struct Vec;
+template <> struct Vec<bf16> { static constexpr int V = 8; };
+template <> struct Vec<float> { static constexpr int V = 4; };
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// Round-to-nearest-even float -> bf16 on the raw bits (NaN kept quiet).
+__device__ __forceinline__ unsigned bf16_bits_rne(float f) {
+  unsigned u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
+  unsigned short b = (unsigned short)bf16_bits_rne(x);
+  return __builtin_bit_cast(bf16, b);
+}
+
+// Store four consecutive values (8 bytes for bf16, 16 bytes for fp32).
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  u32x2 w;
+  w.x = bf16_bits_rne(a) | (bf16_bits_rne(b) << 16);
+  w.y = bf16_bits_rne(c) | (bf16_bits_rne(d) << 16);
+  *reinterpret_cast<u32x2*>(p) = w;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = (f32x4){a, b, c, d};
+}
+
+// Load four consecutive values widened to fp32.
+__device__ __forceinline__ f32x4 load4(const bf16* p) {
+  u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return (f32x4){__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                 __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+}
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
+// Widen one 16-byte chunk of bf16 to 8 floats / of fp32 to 4 floats.
+__device__ __forceinline__ void unpack8(u32x4 w, float* o) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+
+}  // namespace ttt

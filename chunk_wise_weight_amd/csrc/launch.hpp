@@ -1,0 +1,45 @@
+// Host-side launchers of the device kernels (internal to the library).
+// Every launcher assumes its arguments were validated by the C ABI layer.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace ttt {
+
+typedef __bf16 bf16;
+
+template <typename T>
+hipError_t launch_produce_z(const T* H, const T* Wg, const T* Wu, T* Z, int64_t rows, int d, int f, hipStream_t s);
+template <typename T>
+hipError_t launch_produce_vhat(const T* X0, const T* cw, const T* Wt, T* Vh, int64_t rows, int n, int d, int K,
+                               hipStream_t s);
+template <typename T>
+hipError_t launch_chunk_delta(const T* Z, const T* Vh, float* dW, int B, int n, int d, int f, int C, hipStream_t s);
+template <typename T>
+hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
+                             hipStream_t s);
+template <typename T>
+hipError_t launch_chunk_update_scan(const T* Z, const T* Vh, const T* W0, T* Wc, float* Wf, int B, int n, int d,
+                                    int f, int C, float eta, hipStream_t s);
+template <typename T>
+hipError_t launch_apply(const T* Z, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
+                        hipStream_t s);
+template <typename T>
+hipError_t launch_mse_chunk(const T* Z, const T* Vh, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O, T* R, int B,
+                            int n, int d, int f, int C, int c, float eta, hipStream_t s);
+
+// LaCT SwiGLU fast weight (one call runs every chunk of every (batch, head)).
+struct LactArgs {
+  int B, H, n, dh, m, C, order;
+  float eta;
+  const void *q, *k, *v, *W1, *W3, *W2;
+  void* O;
+  float *W1f, *W3f, *W2f;
+  char* ws;
+};
+template <typename T>
+size_t lact_workspace_bytes(int B, int H, int n, int dh, int m, int C);
+template <typename T>
+hipError_t launch_lact(const LactArgs& a, hipStream_t s);
+
+}  // namespace ttt

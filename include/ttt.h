@@ -1,0 +1,196 @@
+/*
+ * ttt.h -- C ABI of the chunk-wise test-time-training fast-weight layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the In-Place TTT form of a gated MLP (source: the review of
+ * "In-Place Test-Time Training", Method §1-§3, eq. (1)-(6)): the MLP's
+ * down-projection W_down is a fast weight.  The sequence is cut into chunks
+ * of C tokens; chunk c is first applied with the state left by chunks
+ * 0..c-1, O_c = Z_c W_c^T (eq. (3)), then one gradient step is folded into
+ * the state (eq. (4)).  Two objectives are provided:
+ *   dot -- negative Frobenius inner product with the target V^ (eq. (6)):
+ *          W_{c+1} = W_c + eta V^_c^T Z_c.  The deltas do not depend on W, so
+ *          all chunks are computed in parallel and combined by an exclusive
+ *          prefix sum (Method §3, three-step form).
+ *   mse -- squared error (1/(2C))||Z_c W^T - V^_c||^2 at the pre-update state:
+ *          W_{c+1} = W_c - (eta/C)(Z_c W_c^T - V^_c)^T Z_c, an in-order scan.
+ * with Z = silu(H W_gate^T) * (H W_up^T) (eq. (2)) and the target
+ * V^ = CausalDepthwiseConv1D(X0) W_target (eq. (5), causal padding of §3).
+ * A LaCT SwiGLU fast weight (review of "Test-Time Training Done Right",
+ * LaCT Model Architecture §1, eq. (3)-(4)) is the second layer family.
+ *
+ * Conventions common to every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller (e.g.
+ *     torch.Tensor.data_ptr()), row-major and contiguous, 16-byte aligned.
+ *     The library allocates nothing; scratch comes from the caller's
+ *     workspace, whose size the matching *_workspace_bytes call returns.
+ *   - Inputs are read only.  Outputs and workspace must not alias inputs or
+ *     each other.  W_down0 is never written: "in place" names the reuse of
+ *     the MLP's own weight as the fast weight, not memory aliasing.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *     the default stream).  The call returns once the work is enqueued.
+ *   - Every argument is validated before any device work is enqueued; on an
+ *     error status nothing has been enqueued and outputs are untouched.  A
+ *     launch failure reported by the runtime returns TTT_ERR_DEVICE, in which
+ *     case outputs are undefined.
+ *   - dtype selects the element type of every activation, weight, Z, V^ and
+ *     O buffer (TTT_F32: fp32 end to end; TTT_BF16: bf16 storage, fp32
+ *     accumulation).  Fast-weight states W_final and dW are always fp32.
+ *   - Each batch row is an independent document whose state starts at
+ *     W_down0 (document-boundary reset, Method §3).
+ *   - Supported sizes: d_model, d_ff and chunk multiples of 8, conv_k in
+ *     1..8 (else TTT_ERR_UNSUPPORTED); seq_len a multiple of chunk (else
+ *     TTT_ERR_SHAPE).  seq_len == 0 or batch == 0 is valid: no output rows,
+ *     W_final rows (if any) equal W_down0.
+ *   - The library keeps no global state; calls with distinct outputs and
+ *     workspaces may run concurrently on different streams.
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  TTT_OK = 0,
+  TTT_ERR_ARG = 1,          /* null pointer, misaligned pointer, unknown mode/order, non-finite eta */
+  TTT_ERR_SHAPE = 2,        /* negative or zero size, seq_len % chunk != 0 */
+  TTT_ERR_DTYPE = 3,        /* dtype not TTT_F32 / TTT_BF16 */
+  TTT_ERR_WORKSPACE = 4,    /* workspace smaller than the query returned, or NULL when needed */
+  TTT_ERR_DEVICE = 5,       /* the HIP runtime rejected a launch */
+  TTT_ERR_UNSUPPORTED = 6   /* valid but outside the sizes this build handles */
+};
+
+enum { TTT_F32 = 0, TTT_BF16 = 1 };
+
+enum {
+  TTT_MODE_DOT = 0,         /* dot objective; delta + prefix sum fused in one MFMA pass when chunk % 64 == 0 */
+  TTT_MODE_MSE = 1,         /* mse objective, in-order chunk scan */
+  TTT_MODE_DOT_SCAN = 2     /* dot objective; every chunk delta materialised, then a device-wide prefix scan */
+};
+
+enum { TTT_UPDATE_THEN_APPLY = 0, TTT_APPLY_THEN_UPDATE = 1 };
+
+/* Sizes of one In-Place layer call.  n = seq_len, d = d_model, f = d_ff,
+ * C = chunk, K = conv_k; k = n / C chunks. */
+typedef struct {
+  int64_t batch, seq_len, d_model, d_ff, chunk, conv_k;
+} ttt_inplace_shape;
+
+/* Sizes of one LaCT layer call: m = hidden (fast MLP width), dh = head_dim. */
+typedef struct {
+  int64_t batch, heads, seq_len, head_dim, hidden, chunk;
+} ttt_lact_shape;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* ttt_status_string(int status);
+
+/* ------------------------------------------------------------------ In-Place TTT layer */
+
+/* Workspace bytes needed by ttt_chunk_apply_update (with_producers = 1) or
+ * ttt_core_apply_update (with_producers = 0) for this shape, dtype and mode.
+ * Writes *bytes; returns a status (same validation as the call itself). */
+int ttt_inplace_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int mode, int with_producers,
+                                size_t* bytes);
+
+/* The whole layer (In-Place TTT review, Method §1-§3):
+ *   Z   = silu(H W_gate^T) * (H W_up^T)                      (eq. (2))
+ *   V^  = CausalDepthwiseConv1D_K(X0) W_target               (eq. (5))
+ *   for each chunk c: O_c = Z_c W_c^T, then the mode's update (eq. (3), (4)/(6)).
+ *
+ *   H, X0     [B, n, d]    dtype   hidden states / token embeddings
+ *   W_gate    [f, d]       dtype   slow weight
+ *   W_up      [f, d]       dtype   slow weight
+ *   W_down0   [d, f]       dtype   pretrained down projection = initial fast weight
+ *   W_target  [d, d]       dtype   indexed [d_in][d_out]: V^ = Y W_target
+ *   conv_w    [d, K]       dtype   depthwise taps, no bias; tap K-1 multiplies the
+ *                                  current token, tap j the token K-1-j steps back,
+ *                                  tokens before the sequence start are zero
+ *   O         [B, n, d]    dtype   output (written)
+ *   W_final   [B, d, f]    fp32    state after the last chunk (written)
+ *   workspace                      >= ttt_inplace_workspace_bytes(..., 1, ...) bytes
+ */
+int ttt_chunk_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, float eta,
+                           const void* H, const void* X0, const void* W_gate, const void* W_up,
+                           const void* W_down0, const void* W_target, const void* conv_w,
+                           void* O, float* W_final, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* The chunk loop alone, given Z [B, n, f] and Vhat [B, n, d] (dtype) instead
+ * of the producers' inputs.  Same outputs and rules as above; workspace from
+ * ttt_inplace_workspace_bytes(..., with_producers = 0, ...). */
+int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, float eta,
+                          const void* Z, const void* Vhat, const void* W_down0,
+                          void* O, float* W_final, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ---- the individual steps (each is one stage of the call above; they compose
+ *      into it and exist for composition and per-step checks) ---- */
+
+/* Slow producer (eq. (2)): Z [B, n, f] = silu(H W_gate^T) * (H W_up^T).
+ * conv_k and chunk of the shape are ignored (chunk must still be > 0). */
+int ttt_produce_z(const ttt_inplace_shape* shape, int dtype, const void* H, const void* W_gate,
+                  const void* W_up, void* Z, void* stream);
+
+/* Target producer (eq. (5), causal padding of Method §3):
+ * Vhat [B, n, d] = CausalDepthwiseConv1D_K(X0) W_target (conventions above). */
+int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, const void* X0, const void* conv_w,
+                     const void* W_target, void* Vhat, void* stream);
+
+/* Per-chunk deltas of the dot objective (Method §3 step 1, eq. (6)):
+ * dW [B, k, d, f] fp32, dW[b, c] = Vhat_c^T Z_c over the chunk's C tokens. */
+int ttt_chunk_delta(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Vhat,
+                    float* dW, void* stream);
+
+/* Exclusive prefix scan over chunks (Method §3 steps 2-3):
+ * Wc [B, k, d, f] dtype, Wc[b, c] = W_down0 + eta * sum_{j<c} dW[b, j];
+ * W_final [B, d, f] fp32 = W_down0 + eta * sum_{j<k} dW[b, j]. */
+int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const void* W_down0,
+                   const float* dW, void* Wc, float* W_final, void* stream);
+
+/* Deltas and scan fused (chunk % 64 == 0 for bf16, % 32 for fp32, else
+ * TTT_ERR_UNSUPPORTED): one MFMA pass over the sequence per output tile whose
+ * fp32 accumulator is the running prefix; at each chunk boundary the tile
+ * writes Wc[b, c] = W_down0 + eta * accumulator.  Same outputs as
+ * ttt_chunk_delta followed by ttt_chunk_scan, without dW. */
+int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, float eta, const void* W_down0,
+                          const void* Z, const void* Vhat, void* Wc, float* W_final, void* stream);
+
+/* Apply (eq. (3)): O [B, n, d], O_c = Z_c Wc[b, c]^T with Wc [B, k, d, f] dtype. */
+int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Wc, void* O,
+                    void* stream);
+
+/* ------------------------------------------------------------------ LaCT SwiGLU layer */
+
+/* Workspace bytes for ttt_lact_swiglu. */
+int ttt_lact_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* bytes);
+
+/* LaCT fast-weight layer (review of "Test-Time Training Done Right", LaCT
+ * Model Architecture §1, eq. (3)-(4); plain GD, one full-chunk step per chunk):
+ *   f_W(x) = W2 [silu(W1 x) * (W3 x)], loss per chunk sum_i (1/2)||f_W(k_i) - v_i||^2,
+ *   W <- W - eta * grad (W1, W2, W3 updated together), o_i = f_W(q_i),
+ *   order: TTT_UPDATE_THEN_APPLY (queries of chunk c see the step taken on
+ *   chunk c) or TTT_APPLY_THEN_UPDATE (they see the state before it).
+ *
+ *   q, k, v   [B, H, n, dh]   dtype
+ *   W1, W3    [H, m, dh]      dtype   initial fast weights (shared by batch rows)
+ *   W2        [H, dh, m]      dtype
+ *   O         [B, H, n, dh]   dtype   (written)
+ *   W1_f, W3_f [B, H, m, dh]  fp32    final states (written)
+ *   W2_f      [B, H, dh, m]   fp32
+ * Supported: head_dim, hidden, chunk multiples of 8; seq_len % chunk == 0. */
+int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta,
+                    const void* q, const void* k, const void* v,
+                    const void* W1, const void* W3, const void* W2,
+                    void* O, float* W1_f, float* W3_f, float* W2_f,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_H */

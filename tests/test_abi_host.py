@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/ttt.h declares, sizes workspaces, and rejects bad
+arguments with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunk_wise_weight_amd as cw
+from chunk_wise_weight_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ttt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cw.lib()
+    declared = _declared()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(declared) == sorted(cw.exported_symbols())
+
+
+def test_status_strings():
+    for st in range(7):
+        assert cw.status_string(st).startswith("TTT_")
+    assert cw.status_string(99) == "unknown status"
+
+
+def _shape(B=1, n=2048, d=256, f=512, C=256, K=4):
+    return cw.InplaceShape(B, n, d, f, C, K)
+
+
+def _ws(shape, dtype=cw.TTT_BF16, mode=cw.TTT_MODE_DOT, prod=1):
+    out = ctypes.c_size_t(0)
+    st = cw.lib().ttt_inplace_workspace_bytes(ctypes.byref(shape), dtype, mode, prod, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_sizes():
+    B, n, d, f, C = 1, 2048, 256, 512, 256
+    k = n // C
+    al = lambda x: (x + 255) // 256 * 256
+    st, nb = _ws(_shape(), cw.TTT_F32, cw.TTT_MODE_DOT, 1)
+    assert st == cw.TTT_OK
+    assert nb == al(B * n * f * 4) + al(B * n * d * 4) + al(B * k * d * f * 4)
+    st, nb = _ws(_shape(), cw.TTT_BF16, cw.TTT_MODE_DOT_SCAN, 0)
+    assert st == cw.TTT_OK and nb == al(B * k * d * f * 2) + al(B * k * d * f * 4)
+    st, nb = _ws(_shape(B=4), cw.TTT_BF16, cw.TTT_MODE_MSE, 0)
+    assert st == cw.TTT_OK and nb == al(4 * C * d * 2) + al(4 * d * f * 2)
+    st, nb = _ws(_shape(B=4), cw.TTT_F32, cw.TTT_MODE_MSE, 0)
+    assert st == cw.TTT_OK and nb == al(4 * C * d * 4)
+    # chunk not a multiple of the 64-element K step: dot falls back to the materialised scan
+    st, nb = _ws(_shape(n=2000, C=40), cw.TTT_BF16, cw.TTT_MODE_DOT, 0)
+    assert st == cw.TTT_OK and nb == al(50 * d * f * 2) + al(50 * d * f * 4)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n=2000, C=256), cw.TTT_ERR_SHAPE),      # seq_len % chunk != 0
+    (dict(C=0), cw.TTT_ERR_SHAPE),
+    (dict(B=-1), cw.TTT_ERR_SHAPE),
+    (dict(d=0), cw.TTT_ERR_SHAPE),
+    (dict(K=0), cw.TTT_ERR_SHAPE),
+    (dict(d=252), cw.TTT_ERR_UNSUPPORTED),        # d % 8
+    (dict(f=500), cw.TTT_ERR_UNSUPPORTED),
+    (dict(n=2044, C=4), cw.TTT_ERR_UNSUPPORTED),  # chunk % 8
+    (dict(K=9), cw.TTT_ERR_UNSUPPORTED),
+])
+def test_shape_errors(kw, status):
+    assert _ws(_shape(**kw))[0] == status
+
+
+def test_dtype_and_mode_errors():
+    assert _ws(_shape(), 7)[0] == cw.TTT_ERR_DTYPE
+    assert _ws(_shape(), cw.TTT_BF16, 9)[0] == cw.TTT_ERR_ARG
+    out = ctypes.c_size_t(0)
+    assert cw.lib().ttt_inplace_workspace_bytes(None, cw.TTT_BF16, 0, 1, ctypes.byref(out)) == cw.TTT_ERR_ARG
+    assert cw.lib().ttt_inplace_workspace_bytes(ctypes.byref(_shape()), cw.TTT_BF16, 0, 1, None) == cw.TTT_ERR_ARG
+
+
+def _fake(addr=0x100000):
+    return ctypes.c_void_p(addr)   # never dereferenced: every call below fails validation first
+
+
+def test_call_rejects_null_and_misaligned_pointers_before_device_work():
+    lib = cw.lib()
+    s = _shape()
+    st, nb = _ws(s, cw.TTT_BF16, cw.TTT_MODE_DOT, 1)
+    p = [_fake() for _ in range(9)]
+    # null H
+    assert lib.ttt_chunk_apply_update(ctypes.byref(s), cw.TTT_BF16, 0, 0.1, None, *p[:8], _fake(), nb, None) == \
+        cw.TTT_ERR_ARG
+    # misaligned O
+    args = [_fake() for _ in range(7)] + [ctypes.c_void_p(0x100004), _fake()]
+    assert lib.ttt_chunk_apply_update(ctypes.byref(s), cw.TTT_BF16, 0, 0.1, *args, _fake(), nb, None) == \
+        cw.TTT_ERR_ARG
+    # workspace too small / missing
+    args = [_fake() for _ in range(9)]
+    assert lib.ttt_chunk_apply_update(ctypes.byref(s), cw.TTT_BF16, 0, 0.1, *args, _fake(), nb - 1, None) == \
+        cw.TTT_ERR_WORKSPACE
+    assert lib.ttt_chunk_apply_update(ctypes.byref(s), cw.TTT_BF16, 0, 0.1, *args, None, nb, None) == \
+        cw.TTT_ERR_WORKSPACE
+    # non-finite eta
+    assert lib.ttt_chunk_apply_update(ctypes.byref(s), cw.TTT_BF16, 0, float("nan"), *args, _fake(), nb, None) == \
+        cw.TTT_ERR_ARG
+    # bad dtype on the core entry point
+    assert lib.ttt_core_apply_update(ctypes.byref(s), 5, 0, 0.1, *[_fake() for _ in range(6)], nb, None) == \
+        cw.TTT_ERR_DTYPE
+
+
+def test_step_entry_points_validate():
+    lib = cw.lib()
+    s = _shape()
+    assert lib.ttt_produce_z(ctypes.byref(s), cw.TTT_BF16, None, _fake(), _fake(), _fake(), None) == cw.TTT_ERR_ARG
+    assert lib.ttt_produce_vhat(ctypes.byref(_shape(K=9)), cw.TTT_BF16, *[_fake()] * 4, None) == \
+        cw.TTT_ERR_UNSUPPORTED
+    assert lib.ttt_chunk_delta(ctypes.byref(_shape(n=100)), cw.TTT_BF16, *[_fake()] * 3, None) == cw.TTT_ERR_SHAPE
+    assert lib.ttt_chunk_scan(ctypes.byref(s), cw.TTT_BF16, float("inf"), *[_fake()] * 4, None) == cw.TTT_ERR_ARG
+    # the fused update-scan needs chunk boundaries on 64-token steps in bf16
+    assert lib.ttt_chunk_update_scan(ctypes.byref(_shape(n=2048, C=32)), cw.TTT_BF16, 0.1, *[_fake()] * 5, None) == \
+        cw.TTT_ERR_UNSUPPORTED
+    assert lib.ttt_chunk_apply(ctypes.byref(s), cw.TTT_BF16, _fake(), None, _fake(), None) == cw.TTT_ERR_ARG
+
+
+def test_lact_validation():
+    lib = cw.lib()
+    out = ctypes.c_size_t(0)
+    good = cw.LactShape(1, 4, 8192, 512, 1024, 4096)
+    assert lib.ttt_lact_workspace_bytes(ctypes.byref(good), cw.TTT_BF16, ctypes.byref(out)) == cw.TTT_OK
+    bad = cw.LactShape(1, 4, 8000, 512, 1024, 4096)
+    assert lib.ttt_lact_workspace_bytes(ctypes.byref(bad), cw.TTT_BF16, ctypes.byref(out)) == cw.TTT_ERR_SHAPE
+    args = [_fake() for _ in range(10)]
+    assert lib.ttt_lact_swiglu(ctypes.byref(good), cw.TTT_BF16, 7, 1.0, *args, _fake(), out.value, None) == \
+        cw.TTT_ERR_ARG
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    H = torch.zeros(1, 16, 8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        cw.ttt_produce_z(H, torch.zeros(8, 8), torch.zeros(8, 8))

@@ -1,0 +1,318 @@
+"""GPU parity of the In-Place TTT layer against the float64 oracle.
+
+Every call goes through the C ABI (ctypes binding).  Inputs come from the
+seeded generators; the oracle sees the same (already rounded) values.
+Tolerances: relative Frobenius <= 1e-4 for fp32 end to end, <= 2e-2 for bf16
+storage with fp32 accumulation (each bf16 rounding of an intermediate costs
+about 2^-9 relative; the layer rounds Z, V^, the applied state and O once
+each, so the expected error is a few 1e-3).
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunk_wise_weight_amd as cw
+import ttt_inputs as ti
+from oracle import inplace as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+STEP_TOL = {"f32": 2e-5, "bf16": 1e-2}
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def dev(inputs):
+    return {k: v.cuda() for k, v in inputs.items()}
+
+
+def small_cfg(dtype, mode, B=1, n=1024, d=264, f=392, C=256, eta=0.05, K=4, seed=7):
+    return ti.InplaceConfig("small", B, n, d, f, C, eta, mode, dtype, conv_k=K, seed=seed)
+
+
+# ---------------------------------------------------------------- individual steps
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_produce_z(dtype):
+    cfg = small_cfg(dtype, "dot", B=2, n=520, d=264, f=392)
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    Z = cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"])
+    torch.cuda.synchronize()
+    ref = orc.gated_intermediate(ti.to_f64(x["H"]).reshape(-1, cfg.d_model), ti.to_f64(x["W_gate"]),
+                                 ti.to_f64(x["W_up"])).reshape(2, 520, 392)
+    assert rel(f64(Z), ref) < STEP_TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,K", [("f32", 4), ("bf16", 4), ("bf16", 1), ("bf16", 3), ("f32", 8)])
+def test_produce_vhat(dtype, K):
+    cfg = small_cfg(dtype, "dot", B=2, n=384, d=328, f=64, K=K)
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    V = cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"])
+    torch.cuda.synchronize()
+    ref = orc.target_values(ti.to_f64(x["X0"]), ti.to_f64(x["conv_w"]), ti.to_f64(x["W_target"]))
+    assert rel(f64(V), ref) < STEP_TOL[dtype]
+
+
+def _zv(dtype, B, n, d, f, seed):
+    gen = torch.Generator().manual_seed(seed)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Z = (torch.randn(B, n, f, generator=gen) * 0.6).to(dt)
+    V = torch.randn(B, n, d, generator=gen).to(dt)
+    W0 = (torch.randn(d, f, generator=gen) / np.sqrt(f)).to(dt)
+    return Z, V, W0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_delta_scan_apply_steps(dtype):
+    B, n, d, f, C, eta = 2, 768, 264, 392, 192, 0.02
+    Z, V, W0 = _zv(dtype, B, n, d, f, 11)
+    Zg, Vg, Wg = Z.cuda(), V.cuda(), W0.cuda()
+    dW = cw.ttt_chunk_delta(Zg, Vg, C)
+    Wc, Wf = cw.ttt_chunk_scan(dW, Wg, eta, C, n)
+    O = cw.ttt_chunk_apply(Zg, Wc, C)
+    torch.cuda.synchronize()
+    Zn, Vn, W0n = f64(Z), f64(V), f64(W0)
+    k = n // C
+    for b in range(B):
+        dref = np.stack([Vn[b, c * C:(c + 1) * C].T @ Zn[b, c * C:(c + 1) * C] for c in range(k)])
+        assert rel(f64(dW[b]), dref) < 1e-5
+        Oref, Wref = orc.chunk_prefix_form(Zn[b], Vn[b], W0n, C, eta)
+        assert rel(f64(Wf[b]), Wref) < 1e-5
+        assert rel(f64(Wf[b]) - W0n, Wref - W0n) < 1e-5
+        pref = np.concatenate([np.zeros((1, d, f)), np.cumsum(dref, axis=0)[:-1]])
+        assert rel(f64(Wc[b]), W0n + eta * pref) < STEP_TOL[dtype]
+        assert rel(f64(O[b]), Oref) < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fused_update_scan_matches_materialised(dtype):
+    B, n, d, f, C, eta = 2, 1024, 264, 520, 256, 0.02
+    Z, V, W0 = _zv(dtype, B, n, d, f, 12)
+    Zg, Vg, Wg = Z.cuda(), V.cuda(), W0.cuda()
+    Wc1, Wf1 = cw.ttt_chunk_update_scan(Zg, Vg, Wg, C, eta)
+    Wc2, Wf2 = cw.ttt_chunk_scan(cw.ttt_chunk_delta(Zg, Vg, C), Wg, eta, C, n)
+    torch.cuda.synchronize()
+    Zn, Vn, W0n = f64(Z), f64(V), f64(W0)
+    for b in range(B):
+        _, Wref = orc.chunk_prefix_form(Zn[b], Vn[b], W0n, C, eta)
+        assert rel(f64(Wf1[b]), Wref) < 1e-5
+        assert rel(f64(Wf1[b]) - W0n, Wref - W0n) < 1e-5
+    assert rel(f64(Wc1), f64(Wc2)) < STEP_TOL[dtype]
+    assert torch.equal(Wc1[:, 0], Wg.expand(B, d, f))      # chunk 0 is applied with W_down0
+
+
+# ---------------------------------------------------------------- whole layer
+
+def run_layer(cfg, mode=None):
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    O, Wf = cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"],
+                                      g["conv_w"], cfg.chunk, cfg.eta, mode or cfg.mode)
+    torch.cuda.synchronize()
+    return x, O, Wf
+
+
+def oracle_layer(cfg, x):
+    mode = "dot" if cfg.mode == "dot_scan" else cfg.mode       # two GPU plans of one objective
+    return orc.inplace_layer(*(ti.to_f64(x[k]) for k in ("H", "X0", "W_gate", "W_up", "W_down0", "W_target",
+                                                           "conv_w")), cfg.chunk, cfg.eta, mode)
+
+
+def check_layer(cfg, x, O, Wf):
+    Oref, Wref = oracle_layer(cfg, x)
+    W0 = ti.to_f64(x["W_down0"])
+    eO, eW, eD = rel(f64(O), Oref), rel(f64(Wf), Wref), rel(f64(Wf) - W0, Wref - W0)
+    tol = TOL[cfg.dtype]
+    assert eO < tol and eW < tol and eD < tol, (eO, eW, eD)
+    return eO, eW, eD
+
+
+def test_layer_fp32_2k_workload():
+    """The fp32 end-to-end workload: batch 1, seq 2048, d 256, d_ff 512, chunk 256, eta 0.1."""
+    cfg = ti.workload("inplace_f32_2k")
+    x, O, Wf = run_layer(cfg)
+    check_layer(cfg, x, O, Wf)
+
+
+@pytest.mark.parametrize("mode", ["dot", "dot_scan"])
+def test_layer_fp32_2k_both_dot_plans(mode):
+    cfg = ti.workload("inplace_f32_2k")
+    x, O, Wf = run_layer(cfg, mode)
+    check_layer(cfg, x, O, Wf)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["dot", "dot_scan", "mse"])
+def test_layer_ragged_multi_tile(dtype, mode):
+    eta = 0.02 if mode != "mse" else 0.5
+    cfg = small_cfg(dtype, mode, B=2, n=1536, d=264, f=392, C=384, eta=eta)
+    x, O, Wf = run_layer(cfg)
+    check_layer(cfg, x, O, Wf)
+
+
+def test_layer_bf16_chunk_not_multiple_of_kstep():
+    # chunk 40: the dot plan falls back to materialised deltas + scan
+    cfg = small_cfg("bf16", "dot", B=1, n=400, d=128, f=256, C=40, eta=0.02)
+    x, O, Wf = run_layer(cfg)
+    check_layer(cfg, x, O, Wf)
+
+
+def test_layer_mse_bf16_workload_shape_reduced():
+    """The MSE workload's structure (batch 4, eta 1, Gaussian inits) at a reduced length."""
+    cfg = ti.workload("mse_bf16_4x64k").with_(seq_len=4096, d_model=512, d_ff=2048, chunk=512)
+    x, O, Wf = run_layer(cfg)
+    check_layer(cfg, x, O, Wf)
+
+
+def test_step_composition_equals_full_call():
+    cfg = small_cfg("bf16", "dot", B=2, n=1024, C=256, eta=0.03)
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    O, Wf = cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"],
+                                      g["conv_w"], cfg.chunk, cfg.eta, "dot")
+    Z = cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"])
+    V = cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"])
+    Wc, Wf2 = cw.ttt_chunk_update_scan(Z, V, g["W_down0"], cfg.chunk, cfg.eta)
+    O2 = cw.ttt_chunk_apply(Z, Wc, cfg.chunk)
+    O3, Wf3 = cw.ttt_core_apply_update(Z, V, g["W_down0"], cfg.chunk, cfg.eta, "dot")
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2) and torch.equal(Wf, Wf2)
+    assert torch.equal(O, O3) and torch.equal(Wf, Wf3)
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_eta_zero_is_plain_gated_mlp(mode):
+    cfg = small_cfg("bf16", mode, n=768, eta=0.0)
+    x, O, Wf = run_layer(cfg)
+    W0 = ti.to_f64(x["W_down0"])
+    assert np.array_equal(f64(Wf[0]), W0)
+    ref = orc.gated_mlp(ti.to_f64(x["H"])[0], ti.to_f64(x["W_gate"]), ti.to_f64(x["W_up"]), W0)
+    assert rel(f64(O[0]), ref) < TOL["bf16"]
+
+
+@pytest.mark.parametrize("mode", ["dot", "dot_scan", "mse"])
+def test_causality_future_rows_do_not_change_past_outputs(mode):
+    cfg = small_cfg("bf16", mode, n=1024, C=256, eta=0.05 if mode != "mse" else 0.5)
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    args = lambda gg: (gg["H"], gg["X0"], gg["W_gate"], gg["W_up"], gg["W_down0"], gg["W_target"], gg["conv_w"])
+    O, _ = cw.ttt_chunk_apply_update(*args(g), cfg.chunk, cfg.eta, mode)
+    c = 1
+    g2 = dict(g)
+    g2["X0"] = g["X0"].clone()
+    g2["X0"][:, c * cfg.chunk:] = torch.randn_like(g2["X0"][:, c * cfg.chunk:], dtype=torch.float32).to(torch.bfloat16)
+    g2["H"] = g["H"].clone()
+    g2["H"][:, (c + 1) * cfg.chunk:] = 0
+    O2, _ = cw.ttt_chunk_apply_update(*args(g2), cfg.chunk, cfg.eta, mode)
+    torch.cuda.synchronize()
+    r = (c + 1) * cfg.chunk
+    assert torch.equal(O[:, :r], O2[:, :r])
+    assert not torch.equal(O[:, r:], O2[:, r:])
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_batch_rows_equal_separate_runs_and_determinism(mode):
+    cfg = small_cfg("bf16", mode, B=3, n=512, C=128, eta=0.05 if mode == "dot" else 0.5)
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    w = (g["W_gate"], g["W_up"], g["W_down0"], g["W_target"], g["conv_w"])
+    O, Wf = cw.ttt_chunk_apply_update(g["H"], g["X0"], *w, cfg.chunk, cfg.eta, mode)
+    O_again, Wf_again = cw.ttt_chunk_apply_update(g["H"], g["X0"], *w, cfg.chunk, cfg.eta, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O_again) and torch.equal(Wf, Wf_again)
+    for b in range(3):
+        Ob, Wb = cw.ttt_chunk_apply_update(g["H"][b:b + 1].contiguous(), g["X0"][b:b + 1].contiguous(), *w,
+                                           cfg.chunk, cfg.eta, mode)
+        torch.cuda.synchronize()
+        assert torch.equal(Ob[0], O[b]) and torch.equal(Wb[0], Wf[b])
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_empty_sequence_and_empty_batch(mode):
+    cfg = small_cfg("bf16", mode, B=2, n=0, C=64)
+    x = ti.inplace_inputs(cfg.with_(seq_len=0))
+    g = dev(x)
+    O, Wf = cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"],
+                                      g["conv_w"], 64, 0.1, mode)
+    torch.cuda.synchronize()
+    assert O.shape == (2, 0, cfg.d_model)
+    assert torch.equal(Wf, g["W_down0"].float().expand(2, -1, -1))
+    g0 = dev(ti.inplace_inputs(cfg.with_(batch=0, seq_len=128)))
+    O, Wf = cw.ttt_chunk_apply_update(g0["H"], g0["X0"], g0["W_gate"], g0["W_up"], g0["W_down0"], g0["W_target"],
+                                      g0["conv_w"], 64, 0.1, mode)
+    assert O.shape[0] == 0 and Wf.shape[0] == 0
+
+
+def test_core_entry_point_orthogonal_keys_reach_target():
+    # chunk = d_ff, Z = sqrt(C) Q (Q orthogonal), V^ = Z W*^T, eta = 1, mse: one step lands on W*
+    f, d = 256, 128
+    rng = np.random.default_rng(5)
+    Q, _ = np.linalg.qr(rng.standard_normal((f, f)))
+    Z = np.sqrt(f) * Q
+    Ws = rng.standard_normal((d, f)) * 0.1
+    V = Z @ Ws.T
+    W0 = rng.standard_normal((d, f)) * 0.1
+    t = lambda a: torch.from_numpy(a).float().cuda()
+    O, Wf = cw.ttt_core_apply_update(t(Z)[None].contiguous(), t(V)[None].contiguous(), t(W0), f, 1.0, "mse")
+    torch.cuda.synchronize()
+    assert rel(f64(Wf[0]), Ws) < 1e-4
+
+
+# ---------------------------------------------------------------- full-size workloads, sampled
+
+def _sampled_full_size(name, n_rows=8, n_entries=16):
+    cfg = ti.workload(name)
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    O, Wf = cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"],
+                                      g["conv_w"], cfg.chunk, cfg.eta, cfg.mode)
+    torch.cuda.synchronize()
+    del g
+    C, d, f = cfg.chunk, cfg.d_model, cfg.d_ff
+    H = ti.to_f64(x["H"])[0]
+    X0 = ti.to_f64(x["X0"])[0]
+    Wg, Wu, W0, Wt, cwt = (ti.to_f64(x[k]) for k in ("W_gate", "W_up", "W_down0", "W_target", "conv_w"))
+    rng = np.random.default_rng(0)
+    # chunks 0 and 1, sampled rows: chunk 1 needs the full delta of chunk 0
+    Z0 = orc.gated_intermediate(H[:C], Wg, Wu)
+    V0 = orc.target_values(X0[:C], cwt, Wt)
+    W1 = W0 + cfg.eta * (V0.T @ Z0)
+    rows0 = np.sort(rng.choice(C, n_rows, replace=False))
+    rows1 = C + np.sort(rng.choice(C, n_rows, replace=False))
+    Og = f64(O[0])
+    assert rel(Og[rows0], Z0[rows0] @ W0.T) < TOL["bf16"]
+    Z1 = orc.gated_intermediate(H[rows1], Wg, Wu)
+    assert rel(Og[rows1], Z1 @ W1.T) < TOL["bf16"]
+    # sampled entries of W_final: W0 + eta * sum over all tokens of V^[t, i] Z[t, j]
+    ii = rng.choice(d, n_entries)
+    jj = rng.choice(f, n_entries)
+    Zcols = orc.silu(H @ Wg[jj].T) * (H @ Wu[jj].T)          # [n, entries]
+    Vcols = orc.causal_depthwise_conv1d(X0, cwt) @ Wt[:, ii]  # [n, entries]
+    ref = W0[ii, jj] + cfg.eta * np.sum(Vcols * Zcols, axis=0)
+    got = f64(Wf[0])[ii, jj]
+    assert rel(got, ref) < TOL["bf16"]
+    assert rel(got - W0[ii, jj], ref - W0[ii, jj]) < TOL["bf16"]
+
+
+@pytest.mark.slow
+def test_full_size_32k_sampled():
+    _sampled_full_size("inplace_bf16_32k")
+
+
+@pytest.mark.slow
+def test_full_size_128k_sampled():
+    _sampled_full_size("inplace_bf16_128k")
