@@ -46,11 +46,12 @@ _SIGNATURES = {
     "ttt_chunk_apply_update": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _S, _P]),
     "ttt_core_apply_update": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _S, _P]),
-    "ttt_produce_z": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P]),
-    "ttt_produce_vhat": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P]),
+    "ttt_produce_z": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P, _P]),
+    "ttt_vhat_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, ctypes.POINTER(_S)]),
+    "ttt_produce_vhat": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _S, _P]),
     "ttt_chunk_delta": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P]),
     "ttt_chunk_scan": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P]),
-    "ttt_chunk_update_scan": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P]),
+    "ttt_chunk_update_scan": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P, _P]),
     "ttt_chunk_apply": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P]),
     "ttt_lact_workspace_bytes": (_I, [ctypes.POINTER(LactShape), _I, ctypes.POINTER(_S)]),
     "ttt_lact_swiglu": (_I, [ctypes.POINTER(LactShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -189,50 +190,62 @@ def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", 
     return O, W_final
 
 
-def ttt_produce_z(H, W_gate, W_up, Z=None):
-    """Z [B, n, f] = silu(H W_gate^T) * (H W_up^T)."""
+def ttt_produce_z(H, W_gate, W_up, Z=None, Zt=None, with_z=True):
+    """Z = silu(H W_gate^T) * (H W_up^T).  Returns (Z [B, n, f] or None, Zt [B, f, n])."""
     B, n, d = H.shape
     f = W_gate.shape[0]
     dt, dev = H.dtype, H.device
     _need(H, "H", (B, n, d), dt, dev)
     _need(W_gate, "W_gate", (f, d), dt, dev)
     _need(W_up, "W_up", (f, d), dt, dev)
-    Z = torch.empty(B, n, f, dtype=dt, device=dev) if Z is None else Z
-    _need(Z, "Z", (B, n, f), dt, dev)
+    if with_z:
+        Z = torch.empty(B, n, f, dtype=dt, device=dev) if Z is None else Z
+        _need(Z, "Z", (B, n, f), dt, dev)
+    Zt = torch.empty(B, f, n, dtype=dt, device=dev) if Zt is None else Zt
+    _need(Zt, "Zt", (B, f, n), dt, dev)
     shape = _inplace_shape(B, n, d, f, max(n, 8), 1)
-    _check(lib().ttt_produce_z(ctypes.byref(shape), _dt(dt), _ptr(H), _ptr(W_gate), _ptr(W_up), _ptr(Z),
-                               _stream(dev)), "ttt_produce_z")
-    return Z
+    _check(lib().ttt_produce_z(ctypes.byref(shape), _dt(dt), _ptr(H), _ptr(W_gate), _ptr(W_up),
+                               _ptr(Z) if with_z else None, _ptr(Zt), _stream(dev)), "ttt_produce_z")
+    return (Z if with_z else None), Zt
 
 
-def ttt_produce_vhat(X0, conv_w, W_target, Vhat=None):
-    """Vhat [B, n, d] = CausalDepthwiseConv1D(X0) W_target."""
+def ttt_vhat_workspace_bytes(shape: InplaceShape, dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().ttt_vhat_workspace_bytes(ctypes.byref(shape), _dt(dtype), ctypes.byref(out)),
+           "ttt_vhat_workspace_bytes")
+    return out.value
+
+
+def ttt_produce_vhat(X0, conv_w, W_target, Vt=None, workspace=None, scale: float = 1.0):
+    """Vt [B, d, n] = scale * (CausalDepthwiseConv1D(X0) W_target)^T."""
     B, n, d = X0.shape
     K = conv_w.shape[1]
     dt, dev = X0.dtype, X0.device
     _need(X0, "X0", (B, n, d), dt, dev)
     _need(conv_w, "conv_w", (d, K), dt, dev)
     _need(W_target, "W_target", (d, d), dt, dev)
-    Vhat = torch.empty(B, n, d, dtype=dt, device=dev) if Vhat is None else Vhat
-    _need(Vhat, "Vhat", (B, n, d), dt, dev)
+    Vt = torch.empty(B, d, n, dtype=dt, device=dev) if Vt is None else Vt
+    _need(Vt, "Vt", (B, d, n), dt, dev)
     shape = _inplace_shape(B, n, d, 8, max(n, 8), K)
-    _check(lib().ttt_produce_vhat(ctypes.byref(shape), _dt(dt), _ptr(X0), _ptr(conv_w), _ptr(W_target), _ptr(Vhat),
-                                  _stream(dev)), "ttt_produce_vhat")
-    return Vhat
+    nbytes = ttt_vhat_workspace_bytes(shape, dt)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib().ttt_produce_vhat(ctypes.byref(shape), _dt(dt), float(scale), _ptr(X0), _ptr(conv_w), _ptr(W_target),
+                                  _ptr(Vt), _ptr(ws), nbytes, _stream(dev)), "ttt_produce_vhat")
+    return Vt
 
 
-def ttt_chunk_delta(Z, Vhat, chunk: int, dW=None):
-    """dW [B, k, d, f] fp32, dW[b, c] = Vhat_c^T Z_c."""
-    B, n, f = Z.shape
-    d = Vhat.shape[2]
-    dt, dev = Z.dtype, Z.device
-    _need(Z, "Z", (B, n, f), dt, dev)
-    _need(Vhat, "Vhat", (B, n, d), dt, dev)
+def ttt_chunk_delta(Zt, Vt, chunk: int, dW=None):
+    """dW [B, k, d, f] fp32, dW[b, c] = Vhat_c^T Z_c, from Zt [B, f, n] and Vt [B, d, n]."""
+    B, f, n = Zt.shape
+    d = Vt.shape[1]
+    dt, dev = Zt.dtype, Zt.device
+    _need(Zt, "Zt", (B, f, n), dt, dev)
+    _need(Vt, "Vt", (B, d, n), dt, dev)
     k = n // chunk if chunk > 0 else 0
     dW = torch.empty(B, k, d, f, dtype=torch.float32, device=dev) if dW is None else dW
     _need(dW, "dW", (B, k, d, f), torch.float32, dev)
     shape = _inplace_shape(B, n, d, f, chunk, 1)
-    _check(lib().ttt_chunk_delta(ctypes.byref(shape), _dt(dt), _ptr(Z), _ptr(Vhat), _ptr(dW), _stream(dev)),
+    _check(lib().ttt_chunk_delta(ctypes.byref(shape), _dt(dt), _ptr(Zt), _ptr(Vt), _ptr(dW), _stream(dev)),
            "ttt_chunk_delta")
     return dW
 
@@ -255,13 +268,14 @@ def ttt_chunk_scan(dW, W_down0, eta: float, chunk: int, seq_len: int, Wc=None, W
     return Wc, W_final
 
 
-def ttt_chunk_update_scan(Z, Vhat, W_down0, chunk: int, eta: float, Wc=None, W_final=None):
-    """Fused deltas + prefix.  Returns (Wc [B, k, d, f] dtype, W_final fp32)."""
-    B, n, f = Z.shape
-    d = Vhat.shape[2]
-    dt, dev = Z.dtype, Z.device
-    _need(Z, "Z", (B, n, f), dt, dev)
-    _need(Vhat, "Vhat", (B, n, d), dt, dev)
+def ttt_chunk_update_scan(Zt, Vt, W_down0, chunk: int, Wc=None, W_final=None):
+    """Fused deltas + prefix from Zt [B, f, n] and the eta-scaled target Vt [B, d, n] (ttt_produce_vhat with
+    scale = eta).  Returns (Wc [B, k, d, f] dtype, W_final fp32)."""
+    B, f, n = Zt.shape
+    d = Vt.shape[1]
+    dt, dev = Zt.dtype, Zt.device
+    _need(Zt, "Zt", (B, f, n), dt, dev)
+    _need(Vt, "Vt", (B, d, n), dt, dev)
     _need(W_down0, "W_down0", (d, f), dt, dev)
     k = n // chunk if chunk > 0 else 0
     Wc = torch.empty(B, k, d, f, dtype=dt, device=dev) if Wc is None else Wc
@@ -269,8 +283,8 @@ def ttt_chunk_update_scan(Z, Vhat, W_down0, chunk: int, eta: float, Wc=None, W_f
     _need(Wc, "Wc", (B, k, d, f), dt, dev)
     _need(W_final, "W_final", (B, d, f), torch.float32, dev)
     shape = _inplace_shape(B, n, d, f, chunk, 1)
-    _check(lib().ttt_chunk_update_scan(ctypes.byref(shape), _dt(dt), float(eta), _ptr(W_down0), _ptr(Z), _ptr(Vhat),
-                                       _ptr(Wc), _ptr(W_final), _stream(dev)), "ttt_chunk_update_scan")
+    _check(lib().ttt_chunk_update_scan(ctypes.byref(shape), _dt(dt), _ptr(W_down0), _ptr(Zt), _ptr(Vt), _ptr(Wc),
+                                       _ptr(W_final), _stream(dev)), "ttt_chunk_update_scan")
     return Wc, W_final
 
 

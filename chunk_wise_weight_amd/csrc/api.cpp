@@ -24,7 +24,8 @@ struct Plan {
   int64_t B, n, d, f, C, K, k;
   size_t esz;
   bool fused;
-  size_t off_Z, off_V, off_Wc, off_dW, off_R, off_Wsh, total;
+  // workspace regions (byte offsets); Z, Y and WtT only with the producers
+  size_t off_Z, off_Y, off_WtT, off_Zt, off_Vt, off_Wc, off_dW, off_Rt, off_Wsh, total;
 };
 
 int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
@@ -34,9 +35,9 @@ int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
     return TTT_ERR_SHAPE;
   if (s->seq_len % s->chunk != 0) return TTT_ERR_SHAPE;
   if (s->d_model % 8 || s->d_ff % 8 || s->chunk % 8 || s->conv_k > 8) return TTT_ERR_UNSUPPORTED;
-  // index and grid ranges the kernels are built for
+  // index, buffer-offset and grid ranges the kernels are built for
   const int64_t lim = (int64_t)1 << 30;
-  if (s->d_model > (1 << 16) || s->d_ff > (1 << 20) || s->seq_len > lim || s->batch > lim ||
+  if (s->d_model > (1 << 16) || s->d_ff > (1 << 20) || s->seq_len > ((int64_t)1 << 22) || s->batch > lim ||
       s->batch * s->seq_len > lim)
     return TTT_ERR_UNSUPPORTED;
   const int64_t rows_tiles = (s->batch * s->seq_len + 255) / 256;
@@ -61,13 +62,19 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   p->fused = mode == TTT_MODE_DOT && p->C % kstep(dtype) == 0;
   const size_t BN = (size_t)p->B * p->n, DF = (size_t)p->d * p->f;
   size_t off = 0;
-  p->off_Z = p->off_V = p->off_Wc = p->off_dW = p->off_R = p->off_Wsh = 0;
+  p->off_Z = p->off_Y = p->off_WtT = p->off_Zt = p->off_Vt = p->off_Wc = p->off_dW = p->off_Rt = p->off_Wsh = 0;
   if (producers) {
     p->off_Z = off;
     off += align_up(BN * p->f * p->esz);
-    p->off_V = off;
+    p->off_Y = off;
     off += align_up(BN * p->d * p->esz);
+    p->off_WtT = off;
+    off += align_up((size_t)p->d * p->d * p->esz);
   }
+  p->off_Zt = off;
+  off += align_up(BN * p->f * p->esz);
+  p->off_Vt = off;
+  off += align_up(BN * p->d * p->esz);
   if (mode == TTT_MODE_DOT || mode == TTT_MODE_DOT_SCAN) {
     p->off_Wc = off;
     off += align_up((size_t)p->B * p->k * DF * p->esz);
@@ -76,7 +83,7 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
       off += align_up((size_t)p->B * p->k * DF * 4);
     }
   } else {
-    p->off_R = off;
+    p->off_Rt = off;
     off += align_up((size_t)p->B * p->C * p->d * p->esz);
     if (dtype == TTT_BF16) {
       p->off_Wsh = off;
@@ -95,11 +102,21 @@ int fill_initial_state(const Plan& p, const void* W0, float* Wf, hipStream_t s) 
   return dev(ttt::launch_chunk_scan<T>(nullptr, (const T*)W0, nullptr, Wf, (int)p.B, 0, (int64_t)p.d * p.f, 0.f, s));
 }
 
+// Scale the target is produced with: the fused dot update takes eta folded
+// into the target (eta V^_c^T Z_c = (eta V^_c)^T Z_c), every other plan takes V^.
+inline float target_scale(const Plan& p, int mode, float eta) {
+  return (mode == TTT_MODE_DOT && p.fused) ? eta : 1.0f;
+}
+
+// The chunk loop, given Z [B, n, f] (for the apply) and its token-contiguous
+// copies Zt [B, f, n], Vt [B, d, n] (for the updates; Vt scaled by
+// target_scale).
 template <typename T>
-int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Vv, const void* W0v, void* Ov,
-             float* Wf, char* ws, hipStream_t s) {
+int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Ztv, const void* Vtv, const void* W0v,
+             void* Ov, float* Wf, char* ws, hipStream_t s) {
   const T* Z = (const T*)Zv;
-  const T* V = (const T*)Vv;
+  const T* Zt = (const T*)Ztv;
+  const T* Vt = (const T*)Vtv;
   const T* W0 = (const T*)W0v;
   T* O = (T*)Ov;
   const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
@@ -107,11 +124,11 @@ int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Vv,
   if (p.B == 0) return TTT_OK;
   if (p.n == 0) return fill_initial_state<T>(p, W0v, Wf, s);
   if (mode == TTT_MODE_MSE) {
-    T* R = (T*)(ws + p.off_R);
+    T* Rt = (T*)(ws + p.off_Rt);
     T* Wsh = p.esz == 2 ? (T*)(ws + p.off_Wsh) : nullptr;
     const T* Wcur = p.esz == 2 ? (const T*)Wsh : (const T*)(const void*)Wf;
     for (int c = 0; c < k; ++c) {
-      int st = dev(ttt::launch_mse_chunk<T>(Z, V, W0, Wcur, Wf, Wsh, O, R, B, n, d, f, C, c, eta, s));
+      int st = dev(ttt::launch_mse_chunk<T>(Z, Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, B, n, d, f, C, c, eta, s));
       if (st != TTT_OK) return st;
     }
     return TTT_OK;
@@ -119,14 +136,30 @@ int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Vv,
   T* Wc = (T*)(ws + p.off_Wc);
   int st;
   if (p.fused) {
-    st = dev(ttt::launch_chunk_update_scan<T>(Z, V, W0, Wc, Wf, B, n, d, f, C, eta, s));
+    st = dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, B, n, d, f, C, s));   // Vt carries eta
   } else {
     float* dW = (float*)(ws + p.off_dW);
-    st = dev(ttt::launch_chunk_delta<T>(Z, V, dW, B, n, d, f, C, s));
+    st = dev(ttt::launch_chunk_delta<T>(Zt, Vt, dW, B, n, d, f, C, s));
     if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, df, eta, s));
   }
   if (st != TTT_OK) return st;
   return dev(ttt::launch_apply<T>(Z, Wc, (int64_t)k * df, df, O, B, n, d, f, C, s));
+}
+
+// Z, Zt and Vt from the producers' inputs.
+template <typename T>
+int run_producers(const Plan& p, const void* H, const void* X0, const void* Wg, const void* Wu, const void* Wt,
+                  const void* cw, char* ws, T* Z, T* Zt, T* Vt, float vscale, hipStream_t s) {
+  const int64_t rows = p.B * p.n;
+  if (rows == 0) return TTT_OK;
+  const int n = (int)p.n, d = (int)p.d, f = (int)p.f;
+  T* Y = (T*)(ws + p.off_Y);
+  T* WtT = (T*)(ws + p.off_WtT);
+  int st = dev(ttt::launch_produce_z<T>((const T*)H, (const T*)Wg, (const T*)Wu, Z, Zt, rows, n, d, f, s));
+  if (st == TTT_OK) st = dev(ttt::launch_conv<T>((const T*)X0, (const T*)cw, Y, rows, n, d, (int)p.K, s));
+  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Wt, WtT, 1, d, d, 1.0f, s));
+  if (st == TTT_OK) st = dev(ttt::launch_produce_vhat<T>(Y, WtT, Vt, rows, n, d, vscale, s));
+  return st;
 }
 
 int check_ws(const Plan& p, void* ws, size_t bytes) {
@@ -136,6 +169,29 @@ int check_ws(const Plan& p, void* ws, size_t bytes) {
 }
 
 inline bool finite(float x) { return isfinite(x); }
+
+template <typename T>
+int layer(const Plan& p, int mode, float eta, const void* H, const void* X0, const void* Wg, const void* Wu,
+          const void* W0, const void* Wt, const void* cw, void* O, float* Wf, char* ws, hipStream_t s) {
+  T* Z = (T*)(ws + p.off_Z);
+  T* Zt = (T*)(ws + p.off_Zt);
+  T* Vt = (T*)(ws + p.off_Vt);
+  int st = run_producers<T>(p, H, X0, Wg, Wu, Wt, cw, ws, Z, Zt, Vt, target_scale(p, mode, eta), s);
+  if (st != TTT_OK) return st;
+  return run_core<T>(p, mode, eta, Z, Zt, Vt, W0, O, Wf, ws, s);
+}
+
+template <typename T>
+int core(const Plan& p, int mode, float eta, const void* Z, const void* V, const void* W0, void* O, float* Wf,
+         char* ws, hipStream_t s) {
+  T* Zt = (T*)(ws + p.off_Zt);
+  T* Vt = (T*)(ws + p.off_Vt);
+  int st = dev(ttt::launch_transpose<T>((const T*)Z, Zt, (int)p.B, (int)p.n, (int)p.f, 1.0f, s));
+  if (st == TTT_OK)
+    st = dev(ttt::launch_transpose<T>((const T*)V, Vt, (int)p.B, (int)p.n, (int)p.d, target_scale(p, mode, eta), s));
+  if (st != TTT_OK) return st;
+  return run_core<T>(p, mode, eta, Z, Zt, Vt, W0, O, Wf, ws, s);
+}
 
 }  // namespace
 
@@ -181,26 +237,9 @@ int ttt_chunk_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, 
   if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  const int64_t rows = p.B * p.n;
-  if (rows > 0) {
-    if (dtype == TTT_BF16) {
-      st = dev(ttt::launch_produce_z<bf16>((const bf16*)H, (const bf16*)W_gate, (const bf16*)W_up,
-                                           (bf16*)(ws + p.off_Z), rows, (int)p.d, (int)p.f, s));
-      if (st == TTT_OK)
-        st = dev(ttt::launch_produce_vhat<bf16>((const bf16*)X0, (const bf16*)conv_w, (const bf16*)W_target,
-                                                (bf16*)(ws + p.off_V), rows, (int)p.n, (int)p.d, (int)p.K, s));
-    } else {
-      st = dev(ttt::launch_produce_z<float>((const float*)H, (const float*)W_gate, (const float*)W_up,
-                                            (float*)(ws + p.off_Z), rows, (int)p.d, (int)p.f, s));
-      if (st == TTT_OK)
-        st = dev(ttt::launch_produce_vhat<float>((const float*)X0, (const float*)conv_w, (const float*)W_target,
-                                                 (float*)(ws + p.off_V), rows, (int)p.n, (int)p.d, (int)p.K, s));
-    }
-    if (st != TTT_OK) return st;
-  }
   if (dtype == TTT_BF16)
-    return run_core<bf16>(p, mode, eta, ws + p.off_Z, ws + p.off_V, W_down0, O, W_final, ws, s);
-  return run_core<float>(p, mode, eta, ws + p.off_Z, ws + p.off_V, W_down0, O, W_final, ws, s);
+    return layer<bf16>(p, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, ws, s);
+  return layer<float>(p, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, ws, s);
 }
 
 int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* Z,
@@ -216,54 +255,88 @@ int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, f
   }
   if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
   hipStream_t s = (hipStream_t)stream;
-  if (dtype == TTT_BF16) return run_core<bf16>(p, mode, eta, Z, Vhat, W_down0, O, W_final, (char*)workspace, s);
-  return run_core<float>(p, mode, eta, Z, Vhat, W_down0, O, W_final, (char*)workspace, s);
+  if (dtype == TTT_BF16) return core<bf16>(p, mode, eta, Z, Vhat, W_down0, O, W_final, (char*)workspace, s);
+  return core<float>(p, mode, eta, Z, Vhat, W_down0, O, W_final, (char*)workspace, s);
 }
 
 int ttt_produce_z(const ttt_inplace_shape* shape, int dtype, const void* H, const void* W_gate, const void* W_up,
-                  void* Z, void* stream) {
+                  void* Z, void* Zt, void* stream) {
   int st = check_inplace_shape(shape, dtype);
   if (st != TTT_OK) return st;
   const int64_t rows = shape->batch * shape->seq_len;
   if (rows == 0) return TTT_OK;
-  if (!ok_ptr(H) || !ok_ptr(W_gate) || !ok_ptr(W_up) || !ok_ptr(Z)) return TTT_ERR_ARG;
+  if (!ok_ptr(H) || !ok_ptr(W_gate) || !ok_ptr(W_up) || !ok_ptr(Zt) || (Z != nullptr && !aligned16(Z)))
+    return TTT_ERR_ARG;
   hipStream_t s = (hipStream_t)stream;
-  const int d = (int)shape->d_model, f = (int)shape->d_ff;
+  const int n = (int)shape->seq_len, d = (int)shape->d_model, f = (int)shape->d_ff;
   if (dtype == TTT_BF16)
-    return dev(ttt::launch_produce_z<bf16>((const bf16*)H, (const bf16*)W_gate, (const bf16*)W_up, (bf16*)Z, rows, d,
-                                           f, s));
-  return dev(ttt::launch_produce_z<float>((const float*)H, (const float*)W_gate, (const float*)W_up, (float*)Z, rows,
-                                          d, f, s));
+    return dev(ttt::launch_produce_z<bf16>((const bf16*)H, (const bf16*)W_gate, (const bf16*)W_up, (bf16*)Z,
+                                           (bf16*)Zt, rows, n, d, f, s));
+  return dev(ttt::launch_produce_z<float>((const float*)H, (const float*)W_gate, (const float*)W_up, (float*)Z,
+                                          (float*)Zt, rows, n, d, f, s));
 }
 
-int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, const void* X0, const void* conv_w,
-                     const void* W_target, void* Vhat, void* stream) {
+int ttt_vhat_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_ARG;
   int st = check_inplace_shape(shape, dtype);
   if (st != TTT_OK) return st;
-  const int64_t rows = shape->batch * shape->seq_len;
-  if (rows == 0) return TTT_OK;
-  if (!ok_ptr(X0) || !ok_ptr(conv_w) || !ok_ptr(W_target) || !ok_ptr(Vhat)) return TTT_ERR_ARG;
-  hipStream_t s = (hipStream_t)stream;
-  const int n = (int)shape->seq_len, d = (int)shape->d_model, K = (int)shape->conv_k;
-  if (dtype == TTT_BF16)
-    return dev(ttt::launch_produce_vhat<bf16>((const bf16*)X0, (const bf16*)conv_w, (const bf16*)W_target,
-                                              (bf16*)Vhat, rows, n, d, K, s));
-  return dev(ttt::launch_produce_vhat<float>((const float*)X0, (const float*)conv_w, (const float*)W_target,
-                                             (float*)Vhat, rows, n, d, K, s));
+  const size_t e = dtype == TTT_BF16 ? 2 : 4;
+  *bytes = align_up((size_t)shape->batch * shape->seq_len * shape->d_model * e) +
+           align_up((size_t)shape->d_model * shape->d_model * e);
+  return TTT_OK;
 }
 
-int ttt_chunk_delta(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Vhat, float* dW,
+int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, float scale, const void* X0, const void* conv_w,
+                     const void* W_target, void* Vt, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  int st = ttt_vhat_workspace_bytes(shape, dtype, &need);
+  if (st != TTT_OK) return st;
+  if (!finite(scale)) return TTT_ERR_ARG;
+  const int64_t rows = shape->batch * shape->seq_len;
+  if (rows == 0) return TTT_OK;
+  if (!ok_ptr(X0) || !ok_ptr(conv_w) || !ok_ptr(W_target) || !ok_ptr(Vt)) return TTT_ERR_ARG;
+  if (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need) return TTT_ERR_WORKSPACE;
+  Plan p{};
+  p.B = shape->batch;
+  p.n = shape->seq_len;
+  p.d = shape->d_model;
+  p.K = shape->conv_k;
+  const size_t e = dtype == TTT_BF16 ? 2 : 4;
+  p.off_Y = 0;
+  p.off_WtT = align_up((size_t)rows * p.d * e);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int n = (int)p.n, d = (int)p.d, K = (int)p.K;
+  if (dtype == TTT_BF16) {
+    st = dev(ttt::launch_conv<bf16>((const bf16*)X0, (const bf16*)conv_w, (bf16*)(ws + p.off_Y), rows, n, d, K, s));
+    if (st == TTT_OK)
+      st = dev(ttt::launch_transpose<bf16>((const bf16*)W_target, (bf16*)(ws + p.off_WtT), 1, d, d, 1.0f, s));
+    if (st == TTT_OK)
+      st = dev(ttt::launch_produce_vhat<bf16>((const bf16*)(ws + p.off_Y), (const bf16*)(ws + p.off_WtT), (bf16*)Vt,
+                                              rows, n, d, scale, s));
+    return st;
+  }
+  st = dev(ttt::launch_conv<float>((const float*)X0, (const float*)conv_w, (float*)(ws + p.off_Y), rows, n, d, K, s));
+  if (st == TTT_OK)
+    st = dev(ttt::launch_transpose<float>((const float*)W_target, (float*)(ws + p.off_WtT), 1, d, d, 1.0f, s));
+  if (st == TTT_OK)
+    st = dev(ttt::launch_produce_vhat<float>((const float*)(ws + p.off_Y), (const float*)(ws + p.off_WtT),
+                                             (float*)Vt, rows, n, d, scale, s));
+  return st;
+}
+
+int ttt_chunk_delta(const ttt_inplace_shape* shape, int dtype, const void* Zt, const void* Vt, float* dW,
                     void* stream) {
   int st = check_inplace_shape(shape, dtype);
   if (st != TTT_OK) return st;
   if (shape->batch * shape->seq_len == 0) return TTT_OK;
-  if (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(dW)) return TTT_ERR_ARG;
+  if (!ok_ptr(Zt) || !ok_ptr(Vt) || !ok_ptr(dW)) return TTT_ERR_ARG;
   hipStream_t s = (hipStream_t)stream;
   const int B = (int)shape->batch, n = (int)shape->seq_len, d = (int)shape->d_model, f = (int)shape->d_ff,
             C = (int)shape->chunk;
   if (dtype == TTT_BF16)
-    return dev(ttt::launch_chunk_delta<bf16>((const bf16*)Z, (const bf16*)Vhat, dW, B, n, d, f, C, s));
-  return dev(ttt::launch_chunk_delta<float>((const float*)Z, (const float*)Vhat, dW, B, n, d, f, C, s));
+    return dev(ttt::launch_chunk_delta<bf16>((const bf16*)Zt, (const bf16*)Vt, dW, B, n, d, f, C, s));
+  return dev(ttt::launch_chunk_delta<float>((const float*)Zt, (const float*)Vt, dW, B, n, d, f, C, s));
 }
 
 int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const void* W_down0, const float* dW,
@@ -284,11 +357,10 @@ int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const v
                                            eta, s));
 }
 
-int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, float eta, const void* W_down0, const void* Z,
-                          const void* Vhat, void* Wc, float* W_final, void* stream) {
+int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void* W_down0, const void* Zt,
+                          const void* Vt, void* Wc, float* W_final, void* stream) {
   int st = check_inplace_shape(shape, dtype);
   if (st != TTT_OK) return st;
-  if (!finite(eta)) return TTT_ERR_ARG;
   if (shape->chunk % kstep(dtype) != 0) return TTT_ERR_UNSUPPORTED;
   if (shape->batch == 0) return TTT_OK;
   if (!ok_ptr(W_down0) || !ok_ptr(W_final)) return TTT_ERR_ARG;
@@ -301,12 +373,12 @@ int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, float eta, 
       return dev(ttt::launch_chunk_scan<bf16>(nullptr, (const bf16*)W_down0, nullptr, W_final, B, 0, df, 0.f, s));
     return dev(ttt::launch_chunk_scan<float>(nullptr, (const float*)W_down0, nullptr, W_final, B, 0, df, 0.f, s));
   }
-  if (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(Wc)) return TTT_ERR_ARG;
+  if (!ok_ptr(Zt) || !ok_ptr(Vt) || !ok_ptr(Wc)) return TTT_ERR_ARG;
   if (dtype == TTT_BF16)
-    return dev(ttt::launch_chunk_update_scan<bf16>((const bf16*)Z, (const bf16*)Vhat, (const bf16*)W_down0, (bf16*)Wc,
-                                                   W_final, B, n, d, f, C, eta, s));
-  return dev(ttt::launch_chunk_update_scan<float>((const float*)Z, (const float*)Vhat, (const float*)W_down0,
-                                                  (float*)Wc, W_final, B, n, d, f, C, eta, s));
+    return dev(ttt::launch_chunk_update_scan<bf16>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)W_down0, (bf16*)Wc,
+                                                   W_final, B, n, d, f, C, s));
+  return dev(ttt::launch_chunk_update_scan<float>((const float*)Zt, (const float*)Vt, (const float*)W_down0,
+                                                  (float*)Wc, W_final, B, n, d, f, C, s));
 }
 
 int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Wc, void* O, void* stream) {

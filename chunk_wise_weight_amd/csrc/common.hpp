@@ -34,12 +34,17 @@ template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
   return __builtin_bit_cast(bf16, b);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ unsigned pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
 // Store four consecutive values (8 bytes for bf16, 16 bytes for fp32).
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
-  u32x2 w;
-  w.x = bf16_bits_rne(a) | (bf16_bits_rne(b) << 16);
-  w.y = bf16_bits_rne(c) | (bf16_bits_rne(d) << 16);
-  *reinterpret_cast<u32x2*>(p) = w;
+  *reinterpret_cast<u32x2*>(p) = (u32x2){pack2_bf16(a, b), pack2_bf16(c, d)};
 }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   *reinterpret_cast<f32x4*>(p) = (f32x4){a, b, c, d};

@@ -1,42 +1,55 @@
 // MFMA tile engine for gfx950 (CDNA4), shared by every contraction of the layer.
 //
-// A workgroup of 256 threads (4 waves of 64) owns a 256 x 256 output tile
-// acc[p][q] = sum_k P[p][k] * Q[q][k] and walks K in steps of 128 bytes
-// (64 bf16 or 32 fp32).  Each wave owns a 128 x 128 quarter held in 16
-// 32x32 MFMA accumulator blocks (256 fp32 per lane, allocated to AGPRs).
+// A workgroup of 256 threads (4 waves of 64) owns a 256 x BQ tile (BQ = 256
+// or 128) acc[p][q] = sum_k P[p][k] * Q[q][k] and walks K in steps of 128
+// bytes (64 bf16 or 32 fp32).  Both operands are K-contiguous in global
+// memory.  Each wave owns a 128 x BQ/2 quarter: 4 x NQB 32x32 MFMA accumulator
+// blocks (NQB = BQ / 64), 64 NQB fp32 per lane, allocated to AGPRs.
 //
-// Both operands are staged in LDS in one layout: ROWS rows of 128 bytes, the
-// 16-byte chunk c of row r stored at slot c ^ (r & 7), so that the 16-byte
-// fragment reads of 8 consecutive rows hit 8 different bank groups.  Two
-// stages of (256 + 256) x 128 B = 128 KB: global loads for step k+1 are in
-// flight (in registers) while step k is multiplied, then written to the other
-// stage; one barrier per step.
+// Global -> LDS: buffer_load_dwordx4 ... lds (LDS DMA).  One instruction moves
+// 64 lanes x 16 B = 8 rows x 128 B of a tile with no VGPR staging.  Out-of-range
+// rows and the K tail are read through a per-lane offset past the buffer
+// resource's range, which the hardware returns as zero: no branches.
 //
-// Global operands come in two layouts, chosen per operand:
-//   * K-contiguous  (element (row, k) at base[row * ld + k]) -- copied as is;
-//   * MN-contiguous (element (row, k) at base[k * ld + row]) -- each thread
-//     loads a V x V block (V = elements per 16 B) and transposes it in
-//     registers before the LDS write, so the MFMA always reads K-packed rows.
+// LDS layout of a tile: 256 rows of 128 B; the 16-byte chunk c of row r sits
+// in slot c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows hit
+// 8 different bank groups.  The DMA reaches this layout by letting lane L of an
+// instruction fetch chunk (L & 7) ^ (L >> 3) of its row.  Two stages of
+// (256 + 256) x 128 B = 128 KB: step k+1 is in flight while step k is
+// multiplied; one barrier per step (LDS: 2 x (256 + BQ) x 128 B).
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, or 4 x v_mfma_f32_32x32x2_f32 for
-// fp32): the P operand feeds the instruction's A slot, Q its B slot, so a lane
-// ends up with one q index and, per group of 4 registers, 4 consecutive p
-// indices.  Epilogues therefore write 4 consecutive p values per store: the
-// output dimension that must be contiguous in memory is always mapped to P.
+// fp32): P feeds the instruction's A slot, Q its B slot.  A lane therefore
+// holds one q index and, per group of 4 registers, 4 consecutive p indices, so
+// epilogues store 4 consecutive p values at once: whichever output dimension
+// is contiguous in memory is mapped to P.
 #pragma once
 #include "common.hpp"
 
 namespace ttt {
 
-constexpr int kThreads = 256;
-constexpr int kTile = 256;          // rows of P and of Q per workgroup
-constexpr int kTileBytes = kTile * 128;
-constexpr int kStageBytes = 2 * kTileBytes;
-constexpr int kSmemBytes = 2 * kStageBytes;
+// GEMM kernels hold 256 accumulators per lane in AGPRs, which caps occupancy at
+// one wave per SIMD anyway; saying so lets the scheduler spend registers on
+// keeping LDS fragment reads ahead of the MFMAs instead of minimising them.
+#define TTT_ONE_WAVE __attribute__((amdgpu_waves_per_eu(1, 1)))
 
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
-}
+constexpr int kThreads = 256;
+constexpr int kTile = 256;                  // rows of the P tile
+constexpr int kTileBytes = kTile * 128;     // bytes of one P tile stage
+constexpr int kSmemBytes = 2 * (kTile + kTile) * 128;   // enough for either tile shape
+
+// Stage layout for a 256 x BQ tile: P tile then Q tile.
+template <int NQB> struct TileShape {
+  static constexpr int BQ = 64 * NQB;
+  static constexpr int kQBytes = BQ * 128;
+  static constexpr int kStage = kTileBytes + kQBytes;
+  static constexpr int kSmem = 2 * kStage;
+};
+constexpr unsigned kOOB = 0x80000000u;     // any offset >= this is outside every resource
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
 
 // ---------------------------------------------------------------- tile scheduling
 
@@ -44,122 +57,77 @@ __device__ __forceinline__ int lds_off(int row, int chunk) {
 // that each XCD receives a contiguous range of logical tile ids: neighbouring
 // tiles (which share operand rows) then share one L2.
 __device__ __forceinline__ int xcd_remap(int bid, int total) {
-  int full = total & ~7;
+  const int full = total & ~7;
   if (bid >= full) return bid;
   return (bid & 7) * (full >> 3) + (bid >> 3);
 }
 
 // Grouped raster over a TP x TQ grid: groups of G q-tiles, p fastest inside a
-// group, so consecutive ids cover a compact G x (ids/G) block.
+// group, so a run of consecutive ids covers a compact block of tiles.
 __device__ __forceinline__ void grouped_tile(int id, int TP, int TQ, int G, int& tp, int& tq) {
-  int per_group = G * TP;
-  int g = id / per_group;
-  int r = id - g * per_group;
-  int rows = min(G, TQ - g * G);
+  const int per_group = G * TP;
+  const int g = id / per_group;
+  const int r = id - g * per_group;
+  const int rows = min(G, TQ - g * G);
   tq = g * G + r % rows;
   tp = r / rows;
 }
 
-// ---------------------------------------------------------------- operand loaders
+// ---------------------------------------------------------------- LDS DMA operands
 
-// K-contiguous operand.  Thread t copies chunk (t & 7) of rows (t >> 3) + 32 i.
-template <typename T>
-struct LoadKC {
-  static constexpr int V = Vec<T>::V;
-  static constexpr int BK = 8 * V;
-  static constexpr int N = kTile * 8 / kThreads;   // 8 chunks per thread
-  u32x4 r[N];
-  const T* rowp[N];   // row start, or nullptr outside the matrix
-  int kc, kmax;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
+  const unsigned n = bytes >= (uint64_t)kOOB ? kOOB - 1u : (unsigned)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+}
 
-  // row_ptr(i) must return the start of tile row i (or nullptr).
-  template <class RowPtr>
-  __device__ __forceinline__ void init(RowPtr row_ptr, int K) {
-    kc = threadIdx.x & 7;
-    kmax = K;
+// Byte offset, inside a 128-byte row, of the chunk this lane fetches.
+__device__ __forceinline__ unsigned dma_chunk_bytes() {
+  const unsigned L = threadIdx.x & 63u;
+  return ((L & 7u) ^ (L >> 3)) << 4;
+}
+
+// K-contiguous operand moved by DMA into a ROWS-row tile.  Plain: instruction
+// i of wave w fills tile rows (ROWS/4) w + 8 i + (0..7) from consecutive rows of
+// one matrix.  DUAL (ROWS = 256): rows come in 32-row blocks alternating between
+// two matrices (instructions 0..3 read the first, 4..7 the second), block pair
+// w holding rows 32 w + (0..31) of both.
+template <bool DUAL, int ROWS = 256>
+struct DmaOp {
+  static constexpr int NI = ROWS / 32;      // DMA instructions per wave
+  static_assert(!DUAL || ROWS == 256, "dual operands fill 256-row tiles");
+  __amdgpu_buffer_rsrc_t rs0, rs1;
+  unsigned off[DUAL ? 4 : NI];
+  unsigned kbytes;
+
+  // rows_valid: rows of this tile inside the matrix; ld_bytes: row pitch.
+  __device__ __forceinline__ void init(const void* base0, const void* base1, int rows_valid, uint64_t ld_bytes,
+                                       unsigned kbytes_) {
+    kbytes = kbytes_;
+    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+    const uint64_t span = rows_valid > 0 ? (uint64_t)(rows_valid - 1) * ld_bytes + kbytes_ : 0;
+    rs0 = make_rsrc(base0, span);
+    rs1 = make_rsrc(DUAL ? base1 : base0, span);
 #pragma unroll
-    for (int i = 0; i < N; ++i) rowp[i] = row_ptr(i * 32 + (threadIdx.x >> 3));
-  }
-  __device__ __forceinline__ void load(int ks) {
-    int k = ks * BK + kc * V;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-      if (rowp[i] != nullptr && k < kmax) v = *reinterpret_cast<const u32x4*>(rowp[i] + k);
-      r[i] = v;
+    for (int i = 0; i < (DUAL ? 4 : NI); ++i) {
+      const int r = DUAL ? w * 32 + i * 8 + (L >> 3) : w * (ROWS / 4) + i * 8 + (L >> 3);
+      off[i] = r < rows_valid ? (unsigned)(r * ld_bytes) : kOOB;
     }
   }
-  __device__ __forceinline__ void store(char* tile) const {
+  __device__ __forceinline__ void issue(int ks, char* tile) const {
+    const unsigned kb = (unsigned)ks * 128u + dma_chunk_bytes();
+    const bool kin = kb < kbytes;
+    char* base = tile + (threadIdx.x >> 6) * NI * 1024;
 #pragma unroll
-    for (int i = 0; i < N; ++i)
-      *reinterpret_cast<u32x4*>(tile + lds_off(i * 32 + (threadIdx.x >> 3), kc)) = r[i];
+    for (int i = 0; i < NI; ++i) {
+      const unsigned o = DUAL ? off[i & 3] : off[i];
+      const unsigned voff = kin ? o + kb : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((DUAL && i >= 4) ? rs1 : rs0, (lds_ptr_t)(base + i * 1024), 16, voff,
+                                               0, 0, 0);
+    }
   }
 };
 
-// Transpose a V x V block held as V rows of 16 bytes.
-__device__ __forceinline__ void transpose_block(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-  // bf16: element c of row s is half (c & 1) of word c >> 1.
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      unsigned a = in[2 * j][c >> 1], b = in[2 * j + 1][c >> 1];
-      out[c][j] = (c & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
-  }
-}
-__device__ __forceinline__ void transpose_block(const u32x4 (&in)[4], u32x4 (&out)[4]) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[c][j] = in[j][c];
-}
-
-// MN-contiguous operand: element (row, k) at base[k * ld + row], rows < rows_valid.
-template <typename T>
-struct LoadMC {
-  static constexpr int V = Vec<T>::V;
-  static constexpr int BK = 8 * V;
-  static constexpr int RB = kTile / V;             // V-blocks along the rows
-  static constexpr int NB = 8 * RB / kThreads;     // blocks per thread (1 bf16, 2 fp32)
-  u32x4 r[NB][V];
-  const T* base;
-  int64_t ld;
-  int rows_valid, kmax;
-
-  __device__ __forceinline__ void init(const T* b, int64_t ld_, int rows, int K) {
-    base = b;
-    ld = ld_;
-    rows_valid = rows;
-    kmax = K;
-  }
-  __device__ __forceinline__ void load(int ks) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      int id = threadIdx.x + kThreads * b;
-      int pb = id % RB, kb = id / RB;
-      int col = pb * V;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        int k = ks * BK + kb * V + v;
-        u32x4 x = (u32x4){0u, 0u, 0u, 0u};
-        if (col < rows_valid && k < kmax) x = *reinterpret_cast<const u32x4*>(base + (int64_t)k * ld + col);
-        r[b][v] = x;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(char* tile) const {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      int id = threadIdx.x + kThreads * b;
-      int pb = id % RB, kb = id / RB;
-      u32x4 t[V];
-      transpose_block(r[b], t);
-#pragma unroll
-      for (int c = 0; c < V; ++c) *reinterpret_cast<u32x4*>(tile + lds_off(pb * V + c, kb)) = t[c];
-    }
-  }
-};
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------- MFMA step
 
@@ -175,72 +143,87 @@ __device__ __forceinline__ void mma(f32x16& acc, u32x4 p, u32x4 q, float*) {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(p[e]), __uint_as_float(q[e]), acc, 0, 0, 0);
 }
 
-template <typename T>
-__device__ __forceinline__ void compute_stage(const char* tp, const char* tq, f32x16 (&acc)[4][4]) {
+template <int NQB>
+__device__ __forceinline__ void load_frags(const char* tp, const char* tq, int g, u32x4 (&pf)[4], u32x4 (&qf)[NQB]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int prow = (w >> 1) * 128 + (lane & 31);
-  const int qrow = (w & 1) * 128 + (lane & 31);
-  const int half = lane >> 5;
+  const int qrow = (w & 1) * (32 * NQB) + (lane & 31);
+  const int chunk = 2 * g + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pf[i] = *reinterpret_cast<const u32x4*>(tp + lds_off(prow + 32 * i, chunk));
+#pragma unroll
+  for (int j = 0; j < NQB; ++j) qf[j] = *reinterpret_cast<const u32x4*>(tq + lds_off(qrow + 32 * j, chunk));
+}
+
+// One K step (four groups of 16 k for bf16 / 8 k for fp32).  Fragments are
+// double-buffered in registers: the LDS reads of group g + 1 are issued before
+// the MFMAs of group g, and scheduling fences keep the compiler from sinking
+// them back next to their use.
+template <typename T, int NQB>
+__device__ __forceinline__ void compute_stage(const char* tp, const char* tq, f32x16 (&acc)[4][NQB]) {
+  u32x4 pf[2][4], qf[2][NQB];
+  load_frags<NQB>(tp, tq, 0, pf[0], qf[0]);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    u32x4 pf[4], qf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pf[i] = *reinterpret_cast<const u32x4*>(tp + lds_off(prow + 32 * i, 2 * g + half));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qf[j] = *reinterpret_cast<const u32x4*>(tq + lds_off(qrow + 32 * j, 2 * g + half));
+    const int cur = g & 1;
+    if (g < 3) load_frags<NQB>(tp, tq, g + 1, pf[cur ^ 1], qf[cur ^ 1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mma(acc[i][j], pf[i], qf[j], (T*)nullptr);
+      for (int j = 0; j < NQB; ++j) mma(acc[i][j], pf[cur][i], qf[cur][j], (T*)nullptr);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 struct NoHook {
-  __device__ __forceinline__ void operator()(int, f32x16 (&)[4][4]) const {}
+  template <int NQB>
+  __device__ __forceinline__ void operator()(int, f32x16 (&)[4][NQB]) const {}
 };
 
-// The main loop: nks steps of BK over K.  hook(ks, acc) runs after step ks
-// (after the barrier; it may touch global memory but not LDS).
-template <typename T, class LP, class LQ, class Hook>
-__device__ __forceinline__ void mainloop(LP& lp, LQ& lq, int nks, f32x16 (&acc)[4][4], char* smem,
-                                         const Hook& hook) {
+template <int NQB>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][NQB]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
+    for (int j = 0; j < NQB; ++j) acc[i][j] = (f32x16){};
+}
+
+// nks steps over K.  hook(ks, acc) runs after step ks, past the barrier; it
+// may read and write global memory but not LDS.
+template <typename T, int NQB, class OP, class OQ, class Hook>
+__device__ __forceinline__ void mainloop(const OP& op, const OQ& oq, int nks, f32x16 (&acc)[4][NQB], char* smem,
+                                         const Hook& hook) {
+  using S = TileShape<NQB>;
   if (nks <= 0) return;
-  lp.load(0);
-  lq.load(0);
-  lp.store(smem);
-  lq.store(smem + kTileBytes);
+  op.issue(0, smem);
+  oq.issue(0, smem + kTileBytes);
+  wait_dma();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
-    char* cur = smem + (ks & 1) * kStageBytes;
-    char* nxt = smem + ((ks & 1) ^ 1) * kStageBytes;
-    const bool more = ks + 1 < nks;
-    if (more) {
-      lp.load(ks + 1);
-      lq.load(ks + 1);
+    char* cur = smem + (ks & 1) * S::kStage;
+    char* nxt = smem + ((ks & 1) ^ 1) * S::kStage;
+    if (ks + 1 < nks) {
+      op.issue(ks + 1, nxt);
+      oq.issue(ks + 1, nxt + kTileBytes);
     }
-    compute_stage<T>(cur, cur + kTileBytes, acc);
-    if (more) {
-      lp.store(nxt);
-      lq.store(nxt + kTileBytes);
-    }
+    compute_stage<T, NQB>(cur, cur + kTileBytes, acc);
+    wait_dma();
     __syncthreads();
     hook(ks, acc);
   }
 }
 
-// Coordinates of this lane's accumulator values: block (i, j), register group
-// g covers p = p0 + pofs(i, g) + 0..3 at q = q0 + qofs(j).
+// Coordinates of this lane's accumulator values inside the tile: block (i, j),
+// register group g covers p = acc_p(i, g) + 0..3 at q = acc_q(j).
 __device__ __forceinline__ int acc_p(int i, int g) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   return (w >> 1) * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
 }
+template <int NQB = 4>
 __device__ __forceinline__ int acc_q(int j) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  return (w & 1) * 128 + j * 32 + (lane & 31);
+  return (w & 1) * (32 * NQB) + j * 32 + (lane & 31);
 }
 
 }  // namespace ttt

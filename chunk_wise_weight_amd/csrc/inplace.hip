@@ -1,218 +1,235 @@
 // In-Place TTT kernels for gfx950: the producers of Z and V^, the dot-objective
 // deltas / prefix scan / fused update-scan, the apply, and the MSE chunk scan.
 // Layer semantics: review of "In-Place Test-Time Training", Method §1-§3.
+//
+// Activation layouts (B batch rows, n tokens, d = d_model, f = d_ff):
+//   Z  [B, n, f]   read by the apply (K = f contiguous)
+//   Zt [B, f, n]   read by the updates (K = tokens contiguous)
+//   Vt [B, d, n]   the target V^, transposed, read by the updates
+// so that every contraction reads both operands K-contiguously.
 #include "gemm.hpp"
 #include "launch.hpp"
 
 namespace ttt {
 
+template <typename T> constexpr int esz() { return (int)sizeof(T); }
+
+// ------------------------------------------------------------------ conv, transpose
+
+// Y = CausalDepthwiseConv1D_KW(X0) (eq. (5) with the causal padding of §3):
+// Y[t, ch] = sum_j conv_w[ch, j] * X0[t - (KW-1) + j, ch], zero before the
+// sequence start.  One thread: 4 consecutive rows x one 16-byte channel chunk.
+template <typename T, int KW>
+__global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T* __restrict__ cw, T* __restrict__ Y,
+                                              int64_t rows, int n, int d) {
+  constexpr int V = Vec<T>::V;
+  const int nchunk = d / V;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= ((rows + 3) / 4) * nchunk) return;
+  const int ch = (int)(gid % nchunk) * V;
+  const int64_t r0 = (gid / nchunk) * 4;
+  float w[V][KW];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(cw + (int64_t)ch * KW);
+#pragma unroll
+    for (int c = 0; c < KW; ++c) {   // V * KW elements = KW chunks of 16 bytes
+      const u32x4 x = src[c];
+      float fv[V];
+      if constexpr (sizeof(T) == 2) unpack8(x, fv);
+      else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fv[e] = __uint_as_float(x[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) w[(c * V + e) / KW][(c * V + e) % KW] = fv[e];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t t = r0 + r;
+    if (t >= rows) break;
+    const int pos = (int)(t % n);
+    float y[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) y[v] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KW; ++j) {
+      const int back = KW - 1 - j;
+      if (pos >= back) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(X0 + (t - back) * d + ch);
+        float xf[V];
+        if constexpr (sizeof(T) == 2) unpack8(x, xf);
+        else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xf[e] = __uint_as_float(x[e]);
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) y[v] = fmaf(w[v][j], xf[v], y[v]);
+      }
+    }
+    u32x4 o;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pack2_bf16(y[2 * e], y[2 * e + 1]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(y[e]);
+    }
+    *reinterpret_cast<u32x4*>(Y + t * d + ch) = o;
+  }
+}
+
+// dst[b][c][r] = scale * src[b][r][c] for an R x C matrix per batch entry (64 x 64 tiles).
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, T* __restrict__ dst, int R, int C,
+                                                   float scale) {
+  __shared__ T tile[64][65];
+  const int64_t b = blockIdx.y;
+  const int tc = (C + 63) / 64;
+  const int r0 = (int)(blockIdx.x / tc) * 64, c0 = (int)(blockIdx.x % tc) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const T* s = src + b * (int64_t)R * C;
+  T* o = dst + b * (int64_t)R * C;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < R && c < C) tile[i][tx] = s[(int64_t)r * C + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < C && r < R) o[(int64_t)c * R + r] = scale == 1.0f ? tile[tx][i] : from_f32<T>(scale * to_f32(tile[tx][i]));
+  }
+}
+
 // ------------------------------------------------------------------ producers
 
-// Z = silu(H W_gate^T) * (H W_up^T)  (eq. (2)).
-// P = rows of W_gate / W_up interleaved in 32-row blocks (gate, up, gate, up,
-// ...): a 256-row P tile covers 128 output columns, and each lane holds the
-// gate and the up value of the same output in blocks i and i + 1.
+// Z = silu(H W_gate^T) * (H W_up^T)  (eq. (2)).  P = tokens, Q = gate and up
+// rows in alternating 32-row blocks, so a lane holds the gate and the up value
+// of one output column in Q blocks jj and jj + 1, for 4 consecutive tokens.
+// Writes Zt[b, j, t..t+3] (packed) and, if Z is given, Z[t + e, j].
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_produce_z(const T* __restrict__ H, const T* __restrict__ Wg,
+__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_produce_z(const T* __restrict__ H, const T* __restrict__ Wg,
                                                          const T* __restrict__ Wu, T* __restrict__ Z,
-                                                         int64_t rows, int d, int f) {
+                                                         T* __restrict__ Zt, int64_t rows, int n, int d, int f) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int TP = (f + 127) / 128;
-  const int TQ = (int)((rows + kTile - 1) / kTile);
+  const int TP = (int)((rows + kTile - 1) / kTile), TQ = (f + 127) / 128;
   int tp, tq;
   grouped_tile(xcd_remap(blockIdx.x, gridDim.x), TP, TQ, 4, tp, tq);
+  const int64_t t0 = (int64_t)tp * kTile;
+  const int j0 = tq * 128;
+  const uint64_t ldb = (uint64_t)d * esz<T>();
 
-  LoadKC<T> lp, lq;
-  lp.init([&](int r) -> const T* {
-    int blk = r >> 5;
-    int j = tp * 128 + (blk >> 1) * 32 + (r & 31);
-    if (j >= f) return nullptr;
-    return ((blk & 1) ? Wu : Wg) + (int64_t)j * d;
-  }, d);
-  lq.init([&](int r) -> const T* {
-    int64_t t = (int64_t)tq * kTile + r;
-    return t < rows ? H + t * d : nullptr;
-  }, d);
+  DmaOp<false> op;
+  op.init(H + t0 * d, nullptr, (int)min<int64_t>(kTile, rows - t0), ldb, (unsigned)ldb);
+  DmaOp<true> oq;
+  oq.init(Wg + (int64_t)j0 * d, Wu + (int64_t)j0 * d, min(128, f - j0), ldb, (unsigned)ldb);
   f32x16 acc[4][4];
-  mainloop<T>(lp, lq, (d + LoadKC<T>::BK - 1) / LoadKC<T>::BK, acc, smem, NoHook{});
+  zero_acc(acc);
+  mainloop<T>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int ii = 0; ii < 4; ii += 2) {
+  for (int jj = 0; jj < 4; jj += 2) {
+    const int j = j0 + ((w & 1) * 2 + (jj >> 1)) * 32 + (lane & 31);
+    if (j >= f) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t row = (int64_t)tq * kTile + acc_q(j);
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = tp * 128 + ((w >> 1) * 2 + (ii >> 1)) * 32 + g * 8 + (lane >> 5) * 4;
-        if (row < rows && col < f) {
-          float z[4];
+        const int64_t row = t0 + acc_p(i, g);
+        if (row >= rows) continue;
+        float z[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) z[e] = silu_f(acc[ii][j][4 * g + e]) * acc[ii + 1][j][4 * g + e];
-          store4(Z + row * f + col, z[0], z[1], z[2], z[3]);
+        for (int e = 0; e < 4; ++e) z[e] = silu_f(acc[i][jj][4 * g + e]) * acc[i][jj + 1][4 * g + e];
+        const int64_t b = row / n, t = row - b * n;
+        store4(Zt + (b * f + j) * (int64_t)n + t, z[0], z[1], z[2], z[3]);
+        if (Z != nullptr) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Z[(row + e) * f + j] = from_f32<T>(z[e]);
         }
       }
     }
   }
 }
 
-// Q-operand loader that forms Y = CausalDepthwiseConv1D_KW(X0) on the fly:
-// chunk (row t, channels ch..ch+V) = sum_j conv_w[ch.., j] * X0[t-(KW-1)+j, ch..],
-// rows before the start of the sequence are zero.
-template <typename T, int KW>
-struct LoadConv {
-  static constexpr int V = Vec<T>::V;
-  static constexpr int BK = 8 * V;
-  static constexpr int N = kTile * 8 / kThreads;
-  u32x4 r[N];
-  const T* rowp[N];
-  int pos[N];
-  const T* convw;
-  int kc, d;
-
-  __device__ __forceinline__ void init(const T* X0, const T* cw, int64_t rows, int n, int d_, int64_t row0) {
-    kc = threadIdx.x & 7;
-    d = d_;
-    convw = cw;
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      int64_t t = row0 + i * 32 + (threadIdx.x >> 3);
-      rowp[i] = t < rows ? X0 + t * d : nullptr;
-      pos[i] = (int)(t % n);
-    }
-  }
-  __device__ __forceinline__ void load(int ks) {
-    const int ch = ks * BK + kc * V;
-    if (ch >= d) {
-#pragma unroll
-      for (int i = 0; i < N; ++i) r[i] = (u32x4){0u, 0u, 0u, 0u};
-      return;
-    }
-    // taps of channels ch..ch+V-1: V * KW contiguous elements of conv_w [d, KW]
-    float w[V][KW];
-    {
-      constexpr int NCH = V * KW / Vec<T>::V;   // 16-byte chunks
-      const u32x4* src = reinterpret_cast<const u32x4*>(convw + (int64_t)ch * KW);
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        u32x4 x = src[c];
-        float f[Vec<T>::V];
-        if constexpr (sizeof(T) == 2) unpack8(x, f);
-        else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(x[e]);
-        }
-#pragma unroll
-        for (int e = 0; e < Vec<T>::V; ++e) {
-          const int idx = c * Vec<T>::V + e;
-          w[idx / KW][idx % KW] = f[e];
-        }
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      float y[V];
-#pragma unroll
-      for (int v = 0; v < V; ++v) y[v] = 0.f;
-      if (rowp[i] != nullptr) {
-#pragma unroll
-        for (int j = 0; j < KW; ++j) {
-          const int back = KW - 1 - j;
-          if (pos[i] >= back) {
-            u32x4 x = *reinterpret_cast<const u32x4*>(rowp[i] - (int64_t)back * d + ch);
-            float xf[V];
-            if constexpr (sizeof(T) == 2) unpack8(x, xf);
-            else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) xf[e] = __uint_as_float(x[e]);
-            }
-#pragma unroll
-            for (int v = 0; v < V; ++v) y[v] = fmaf(w[v][j], xf[v], y[v]);
-          }
-        }
-      }
-      u32x4 o;
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = bf16_bits_rne(y[2 * e]) | (bf16_bits_rne(y[2 * e + 1]) << 16);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(y[e]);
-      }
-      r[i] = o;
-    }
-  }
-  __device__ __forceinline__ void store(char* tile) const {
-#pragma unroll
-    for (int i = 0; i < N; ++i)
-      *reinterpret_cast<u32x4*>(tile + lds_off(i * 32 + (threadIdx.x >> 3), kc)) = r[i];
-  }
-};
-
-// V^ = Conv1D(X0) W_target  (eq. (5)); W_target [d_in, d_out] is read
-// MN-contiguously as the P operand (rows = output channels).
-template <typename T, int KW>
-__global__ __launch_bounds__(kThreads) void k_produce_vhat(const T* __restrict__ X0, const T* __restrict__ convw,
-                                                            const T* __restrict__ Wt, T* __restrict__ Vh,
-                                                            int64_t rows, int n, int d) {
+// Vt = scale * (Y W_target)^T with WtT = W_target^T [d_out, d_in].  P = tokens,
+// Q = output channels; writes Vt[b, o, t..t+3].
+template <typename T>
+__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_produce_vhat(const T* __restrict__ Y, const T* __restrict__ WtT,
+                                                            T* __restrict__ Vt, int64_t rows, int n, int d,
+                                                            float scale) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int TP = (d + kTile - 1) / kTile;
-  const int TQ = (int)((rows + kTile - 1) / kTile);
+  const int TP = (int)((rows + kTile - 1) / kTile), TQ = (d + kTile - 1) / kTile;
   int tp, tq;
   grouped_tile(xcd_remap(blockIdx.x, gridDim.x), TP, TQ, 4, tp, tq);
+  const int64_t t0 = (int64_t)tp * kTile;
+  const int o0 = tq * kTile;
+  const uint64_t ldb = (uint64_t)d * esz<T>();
 
-  LoadMC<T> lp;
-  lp.init(Wt + tp * kTile, d, d - tp * kTile, d);
-  LoadConv<T, KW> lq;
-  lq.init(X0, convw, rows, n, d, (int64_t)tq * kTile);
+  DmaOp<false> op, oq;
+  op.init(Y + t0 * d, nullptr, (int)min<int64_t>(kTile, rows - t0), ldb, (unsigned)ldb);
+  oq.init(WtT + (int64_t)o0 * d, nullptr, min(kTile, d - o0), ldb, (unsigned)ldb);
   f32x16 acc[4][4];
-  mainloop<T>(lp, lq, (d + LoadKC<T>::BK - 1) / LoadKC<T>::BK, acc, smem, NoHook{});
+  zero_acc(acc);
+  mainloop<T>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int o = o0 + acc_q(j);
+    if (o >= d) continue;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t row = (int64_t)tq * kTile + acc_q(j);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = tp * kTile + acc_p(i, g);
-        if (row < rows && col < d)
-          store4(Vh + row * d + col, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        const int64_t row = t0 + acc_p(i, g);
+        if (row >= rows) continue;
+        const int64_t b = row / n, t = row - b * n;
+        store4(Vt + (b * d + o) * (int64_t)n + t, scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1],
+               scale * acc[i][j][4 * g + 2], scale * acc[i][j][4 * g + 3]);
       }
-    }
+  }
 }
 
-// ------------------------------------------------------------------ dot objective: deltas, scan
+// ------------------------------------------------------------------ dot objective
 
-// Writes base[q][p] = w0[q][p] + eta * acc for this lane's values (ld = f).
-template <typename T, typename TO>
-__device__ __forceinline__ void write_state(const f32x16 (&acc)[4][4], const T* __restrict__ W0, TO* __restrict__ out,
-                                            int tp, int tq, int d, int f, float eta) {
+// Visit this lane's accumulator quads of a [d_model x d_ff] state tile (P = j,
+// d_ff, contiguous; Q = i, d_model) with one row pointer per Q block plus
+// small constant offsets.  fn(row_offset_elems, dj, ib, jb, g) is called for
+// every quad inside the matrix.
+template <int NQB, class Fn>
+__device__ __forceinline__ void for_state_quads(int j0, int i0, int d, int f, Fn&& fn) {
+  const bool full = j0 + kTile <= f && i0 + 64 * NQB <= d;
+  const int pl = acc_p(0, 0), ql = acc_q<NQB>(0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int jb = 0; jb < NQB; ++jb) {
+    const int i = i0 + ql + jb * 32;
+    const int64_t rowoff = (int64_t)i * f + j0 + pl;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = tq * kTile + acc_q(j);
+    for (int ib = 0; ib < 4; ++ib) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int p = tp * kTile + acc_p(i, g);
-        if (q < d && p < f) {
-          const int64_t o = (int64_t)q * f + p;
-          f32x4 w = load4(W0 + o);
-          store4(out + o, fmaf(eta, acc[i][j][4 * g], w[0]), fmaf(eta, acc[i][j][4 * g + 1], w[1]),
-                 fmaf(eta, acc[i][j][4 * g + 2], w[2]), fmaf(eta, acc[i][j][4 * g + 3], w[3]));
-        }
+        const int dj = ib * 32 + g * 8;
+        if (full || (i < d && j0 + pl + dj < f)) fn(rowoff, dj, ib, jb, g);
       }
-      __builtin_amdgcn_sched_barrier(0);   // one block at a time: bounds the live W0 loads
+      __builtin_amdgcn_sched_barrier(0);   // one 32x32 block at a time
     }
+  }
 }
 
-// Per-chunk delta dW[b, c] = V^_c^T Z_c (Method §3, step 1).  P = d_ff (Z
-// columns), Q = d_model (V^ columns), K = the chunk's tokens; both operands are
-// token-major, hence MN-contiguous.
+template <int NQB, typename TO>
+__device__ __forceinline__ void store_state(const f32x16 (&acc)[4][NQB], TO* __restrict__ out, int j0, int i0, int d,
+                                            int f) {
+  for_state_quads<NQB>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+    const f32x16& blk = acc[ib][jb];
+    store4(out + ro + dj, blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]);
+  });
+}
+
+// Per-chunk delta dW[b, c] = V^_c^T Z_c (Method §3, step 1), fp32 [B, k, d, f].
+// P = d_ff rows of Zt, Q = d_model rows of Vt, K = the chunk's C tokens.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_chunk_delta(const T* __restrict__ Z, const T* __restrict__ Vh,
-                                                           float* __restrict__ dW, int B, int n, int d, int f, int C) {
+__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_chunk_delta(const T* __restrict__ Zt, const T* __restrict__ Vt,
+                                                           float* __restrict__ dW, int n, int d, int f, int C) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   const int TP = (f + kTile - 1) / kTile, TQ = (d + kTile - 1) / kTile;
   const int per = TP * TQ;
@@ -222,33 +239,37 @@ __global__ __launch_bounds__(kThreads) void k_chunk_delta(const T* __restrict__ 
   grouped_tile(id - bc * per, TP, TQ, 4, tp, tq);
   const int k = n / C;
   const int b = bc / k, c = bc - b * k;
-  const int64_t row0 = (int64_t)b * n + (int64_t)c * C;
+  const int j0 = tp * kTile, i0 = tq * kTile;
+  const uint64_t ldb = (uint64_t)n * esz<T>();
+  const unsigned kbytes = (unsigned)C * esz<T>();
 
-  LoadMC<T> lp, lq;
-  lp.init(Z + row0 * f + tp * kTile, f, f - tp * kTile, C);
-  lq.init(Vh + row0 * d + tq * kTile, d, d - tq * kTile, C);
+  DmaOp<false> op, oq;
+  op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C, nullptr, min(kTile, f - j0), ldb, kbytes);
+  oq.init(Vt + ((int64_t)b * d + i0) * n + (int64_t)c * C, nullptr, min(kTile, d - i0), ldb, kbytes);
   f32x16 acc[4][4];
-  mainloop<T>(lp, lq, (C + LoadMC<T>::BK - 1) / LoadMC<T>::BK, acc, smem, NoHook{});
+  zero_acc(acc);
+  mainloop<T>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
 
   float* out = dW + (int64_t)bc * d * f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int jb = 0; jb < 4; ++jb) {
+    const int i = i0 + acc_q(jb);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = tq * kTile + acc_q(j);
+    for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int p = tp * kTile + acc_p(i, g);
-        if (q < d && p < f)
-          store4(out + (int64_t)q * f + p, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        const int j = j0 + acc_p(ib, g);
+        if (i < d && j < f)
+          store4(out + (int64_t)i * f + j, acc[ib][jb][4 * g], acc[ib][jb][4 * g + 1], acc[ib][jb][4 * g + 2],
+                 acc[ib][jb][4 * g + 3]);
       }
-    }
+  }
 }
 
 // Exclusive prefix scan over chunks (Method §3, steps 2-3), four elements per
 // thread: Wc[b, c] = W0 + eta * sum_{j<c} dW[b, j]; W_final = W0 + eta * sum_all.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_chunk_scan(const float* __restrict__ dW, const T* __restrict__ W0,
+__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_chunk_scan(const float* __restrict__ dW, const T* __restrict__ W0,
                                                           T* __restrict__ Wc, float* __restrict__ Wf, int k,
                                                           int64_t df, float eta) {
   const int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
@@ -267,65 +288,70 @@ __global__ __launch_bounds__(kThreads) void k_chunk_scan(const float* __restrict
          fmaf(eta, s[3], w0[3]));
 }
 
-// Fused delta + scan: each workgroup owns one [256 d_model x 256 d_ff] tile of
-// the state and runs its K loop over the whole sequence in token order; the
-// accumulator is the running sum of the deltas, so at every chunk boundary it
-// is exactly the exclusive prefix of the next chunk.
+// Fused delta + scan: each workgroup owns one [256 d_ff x 256 d_model] tile of
+// the state and runs its K loop over the whole sequence in token order.  The
+// accumulator starts at W_down0 and the target arrives pre-scaled by eta
+// (Vt = eta V^^T: eta times a delta equals the delta of eta times the target),
+// so after the tokens of chunks 0..c-1 it holds exactly W_c, the state chunk c
+// is applied with.  At each chunk boundary the tile is stored in the operand
+// dtype; after the last chunk in fp32 as W_final.
 template <typename T>
 struct SnapshotHook {
-  const T* W0;
   T* Wc;              // [k, d, f] of this batch row
-  int steps_per_chunk, k, tp, tq, d, f;
-  float eta;
-  __device__ __forceinline__ void operator()(int ks, f32x16 (&acc)[4][4]) const {
+  int steps_per_chunk, k, j0, i0, d, f;
+  template <int NQB>
+  __device__ __forceinline__ void operator()(int ks, f32x16 (&acc)[4][NQB]) const {
     const int done = ks + 1;
     if (done % steps_per_chunk != 0) return;
     const int c = done / steps_per_chunk;
     if (c >= k) return;
-    write_state(acc, W0, Wc + (int64_t)c * d * f, tp, tq, d, f, eta);
+    store_state<NQB>(acc, Wc + (int64_t)c * d * f, j0, i0, d, f);
   }
 };
 
+// Tile: 256 d_ff (P) x 128 d_model (Q).  The smaller accumulator (128 per lane)
+// leaves room in registers for the snapshot stores inside the K loop.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_chunk_update_scan(const T* __restrict__ Z, const T* __restrict__ Vh,
+__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_chunk_update_scan(const T* __restrict__ Zt, const T* __restrict__ Vt,
                                                                  const T* __restrict__ W0, T* __restrict__ Wc,
-                                                                 float* __restrict__ Wf, int B, int n, int d, int f,
-                                                                 int C, float eta) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int TP = (f + kTile - 1) / kTile, TQ = (d + kTile - 1) / kTile;
+                                                                 float* __restrict__ Wf, int n, int d, int f, int C) {
+  constexpr int NQB = 2, BQ = 128;
+  __shared__ __attribute__((aligned(16))) char smem[TileShape<NQB>::kSmem];
+  const int TP = (f + kTile - 1) / kTile, TQ = (d + BQ - 1) / BQ;
   const int per = TP * TQ;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int b = id / per;
   int tp, tq;
   grouped_tile(id - b * per, TP, TQ, 4, tp, tq);
   const int k = n / C;
-  const int64_t row0 = (int64_t)b * n;
+  const int j0 = tp * kTile, i0 = tq * BQ;
+  const uint64_t ldb = (uint64_t)n * esz<T>();
   T* wc = Wc + (int64_t)b * k * d * f;
 
-  LoadMC<T> lp, lq;
-  lp.init(Z + row0 * f + tp * kTile, f, f - tp * kTile, n);
-  lq.init(Vh + row0 * d + tq * kTile, d, d - tq * kTile, n);
-  f32x16 acc[4][4];
+  DmaOp<false> op;
+  op.init(Zt + ((int64_t)b * f + j0) * n, nullptr, min(kTile, f - j0), ldb, (unsigned)ldb);
+  DmaOp<false, BQ> oq;
+  oq.init(Vt + ((int64_t)b * d + i0) * n, nullptr, min(BQ, d - i0), ldb, (unsigned)ldb);
+  f32x16 acc[4][NQB];
+  zero_acc(acc);
+  for_state_quads<NQB>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+    const f32x4 w = load4(W0 + ro + dj);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x16){};
-  write_state(acc, W0, wc, tp, tq, d, f, 0.f);                        // chunk 0: W_down0
-  SnapshotHook<T> hook{W0, wc, C / LoadMC<T>::BK, k, tp, tq, d, f, eta};
-  mainloop<T>(lp, lq, n / LoadMC<T>::BK, acc, smem, hook);
-  write_state(acc, W0, Wf + (int64_t)b * d * f, tp, tq, d, f, eta);  // after the last chunk
+    for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
+  });
+  store_state<NQB>(acc, wc, j0, i0, d, f);                                  // chunk 0: W_down0
+  const SnapshotHook<T> hook{wc, C * esz<T>() / 128, k, j0, i0, d, f};
+  mainloop<T>(op, oq, (int)(ldb / 128), acc, smem, hook);
+  store_state<NQB>(acc, Wf + (int64_t)b * d * f, j0, i0, d, f);            // after the last chunk
 }
 
 // ------------------------------------------------------------------ apply
 
-// O_c = Z_c W^T for every chunk (eq. (3)).  P = d_model (rows of W), Q = the
-// chunk's tokens, K = d_ff; both operands K-contiguous.  W of (b, c) is
-// W + b * wsb + c * wsc.  With MSE, also R_c = O_c - V^_c into R [B, C, d].
-template <typename T, bool MSE>
-__global__ __launch_bounds__(kThreads) void k_apply(const T* __restrict__ Z, const T* __restrict__ W, int64_t wsb,
-                                                     int64_t wsc, T* __restrict__ O, const T* __restrict__ Vh,
-                                                     T* __restrict__ R, int n, int d, int f, int C, int nch,
-                                                     int c_first) {
+// O_c = Z_c W^T for every chunk (eq. (3)).  P = d_model rows of W, Q = the
+// chunk's tokens, K = d_ff.  W of (b, c) is W + b * wsb + c * wsc.
+template <typename T>
+__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_apply(const T* __restrict__ Z, const T* __restrict__ W, int64_t wsb,
+                                                     int64_t wsc, T* __restrict__ O, int n, int d, int f, int C) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
   const int TP = (d + kTile - 1) / kTile, TQ = (C + kTile - 1) / kTile;
   const int per = TP * TQ;
@@ -333,51 +359,90 @@ __global__ __launch_bounds__(kThreads) void k_apply(const T* __restrict__ Z, con
   const int bc = id / per;
   int tp, tq;
   grouped_tile(id - bc * per, TP, TQ, 4, tp, tq);
-  const int b = bc / nch, c = c_first + (bc - b * nch);
-  const T* Wbc = W + (int64_t)b * wsb + (int64_t)c * wsc;
-  const int64_t row0 = (int64_t)b * n + (int64_t)c * C;
+  const int k = n / C;
+  const int b = bc / k, c = bc - b * k;
+  const int i0 = tp * kTile, t0 = tq * kTile;
+  const int64_t row0 = (int64_t)b * n + (int64_t)c * C + t0;
+  const uint64_t ldb = (uint64_t)f * esz<T>();
 
-  LoadKC<T> lp, lq;
-  lp.init([&](int r) -> const T* {
-    int i = tp * kTile + r;
-    return i < d ? Wbc + (int64_t)i * f : nullptr;
-  }, f);
-  lq.init([&](int r) -> const T* {
-    int t = tq * kTile + r;
-    return t < C ? Z + (row0 + t) * f : nullptr;
-  }, f);
+  DmaOp<false> op, oq;
+  op.init(W + (int64_t)b * wsb + (int64_t)c * wsc + (int64_t)i0 * f, nullptr, min(kTile, d - i0), ldb,
+          (unsigned)ldb);
+  oq.init(Z + row0 * f, nullptr, min(kTile, C - t0), ldb, (unsigned)ldb);
   f32x16 acc[4][4];
-  mainloop<T>(lp, lq, (f + LoadKC<T>::BK - 1) / LoadKC<T>::BK, acc, smem, NoHook{});
+  zero_acc(acc);
+  mainloop<T>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
+  const bool full = i0 + kTile <= d && t0 + kTile <= C;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int j = 0; j < 4; ++j) {
+    const int t = acc_q(j);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = tq * kTile + acc_q(j);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int p = tp * kTile + acc_p(i, g);
-        if (t < C && p < d) {
-          const int64_t o = (row0 + t) * d + p;
-          store4(O + o, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          if constexpr (MSE) {
-            f32x4 v = load4(Vh + o);
-            store4(R + ((int64_t)b * C + t) * d + p, acc[i][j][4 * g] - v[0], acc[i][j][4 * g + 1] - v[1],
-                   acc[i][j][4 * g + 2] - v[2], acc[i][j][4 * g + 3] - v[3]);
-          }
-        }
+        const int p = i0 + acc_p(i, g);
+        if (full || (t0 + t < C && p < d))
+          store4(O + (row0 + t) * d + p, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                 acc[i][j][4 * g + 3]);
       }
-    }
+  }
 }
 
-// ------------------------------------------------------------------ MSE objective: state update
+// ------------------------------------------------------------------ MSE objective
 
-// W_{c+1} = W_c - (eta / C) R_c^T Z_c with R_c = Z_c W_c^T - V^_c (eq. (4) with
-// the squared error at the pre-update state).  P = d_ff, Q = d_model, K = the
-// chunk's tokens.  The fp32 state lives in Ws [B, d, f]; for c == 0 the previous
-// state is W_down0.  Wsh (may be null) receives a dtype copy for the next apply.
+// Apply of chunk c with the current state and the residual of its squared error:
+// O_c = Z_c W^T, Rt[b] = (O_c - V^_c)^T [B, d, C].  P = the chunk's tokens,
+// Q = d_model rows of W (W_down0 for c == 0, else this row's state copy).
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_mse_update(const T* __restrict__ Z, const T* __restrict__ R,
+__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_mse_apply(const T* __restrict__ Z, const T* __restrict__ W, int64_t wsb,
+                                                         T* __restrict__ O, const T* __restrict__ Vt,
+                                                         T* __restrict__ Rt, int n, int d, int f, int C, int c) {
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
+  const int TP = (C + kTile - 1) / kTile, TQ = (d + kTile - 1) / kTile;
+  const int per = TP * TQ;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = id / per;
+  int tp, tq;
+  grouped_tile(id - b * per, TP, TQ, 4, tp, tq);
+  const int t0 = tp * kTile, i0 = tq * kTile;
+  const int64_t row0 = (int64_t)b * n + (int64_t)c * C;
+  const uint64_t ldb = (uint64_t)f * esz<T>();
+
+  DmaOp<false> op, oq;
+  op.init(Z + (row0 + t0) * f, nullptr, min(kTile, C - t0), ldb, (unsigned)ldb);
+  oq.init(W + (int64_t)b * wsb + (int64_t)i0 * f, nullptr, min(kTile, d - i0), ldb, (unsigned)ldb);
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  mainloop<T>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
+
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = i0 + acc_q(j);
+    if (i >= d) continue;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int t = t0 + acc_p(ib, g);
+        if (t >= C) continue;
+        float a[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = acc[ib][j][4 * g + e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[(row0 + t + e) * d + i] = from_f32<T>(a[e]);
+        const f32x4 v = load4(Vt + ((int64_t)b * d + i) * n + (int64_t)c * C + t);
+        store4(Rt + ((int64_t)b * d + i) * C + t, a[0] - v[0], a[1] - v[1], a[2] - v[2], a[3] - v[3]);
+      }
+  }
+}
+
+// W_{c+1} = W_c - (eta / C) R_c^T Z_c (eq. (4) with the squared error at the
+// pre-update state).  P = d_ff rows of Zt (the chunk's tokens), Q = d_model rows
+// of Rt, K = C.  The fp32 state lives in Ws [B, d, f] (W_down0 before chunk 0);
+// Wsh (may be null) receives a dtype copy for the next apply.
+template <typename T>
+__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_mse_update(const T* __restrict__ Zt, const T* __restrict__ Rt,
                                                           const T* __restrict__ W0, float* __restrict__ Ws,
                                                           T* __restrict__ Wsh, int n, int d, int f, int C, int c,
                                                           float scale) {
@@ -388,57 +453,52 @@ __global__ __launch_bounds__(kThreads) void k_mse_update(const T* __restrict__ Z
   const int b = id / per;
   int tp, tq;
   grouped_tile(id - b * per, TP, TQ, 4, tp, tq);
-  const int64_t row0 = (int64_t)b * n + (int64_t)c * C;
+  const int j0 = tp * kTile, i0 = tq * kTile;
+  const unsigned kbytes = (unsigned)C * esz<T>();
 
-  LoadMC<T> lp, lq;
-  lp.init(Z + row0 * f + tp * kTile, f, f - tp * kTile, C);
-  lq.init(R + (int64_t)b * C * d + tq * kTile, d, d - tq * kTile, C);
+  DmaOp<false> op, oq;
+  op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C, nullptr, min(kTile, f - j0), (uint64_t)n * esz<T>(),
+          kbytes);
+  oq.init(Rt + ((int64_t)b * d + i0) * C, nullptr, min(kTile, d - i0), (uint64_t)kbytes, kbytes);
   f32x16 acc[4][4];
-  mainloop<T>(lp, lq, (C + LoadMC<T>::BK - 1) / LoadMC<T>::BK, acc, smem, NoHook{});
+  zero_acc(acc);
+  mainloop<T>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
 
   float* ws = Ws + (int64_t)b * d * f;
   T* wsh = Wsh ? Wsh + (int64_t)b * d * f : nullptr;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int jb = 0; jb < 4; ++jb) {
+    const int i = i0 + acc_q(jb);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int q = tq * kTile + acc_q(j);
+    for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int p = tp * kTile + acc_p(i, g);
-        if (q < d && p < f) {
-          const int64_t o = (int64_t)q * f + p;
-          f32x4 w = (c == 0) ? load4(W0 + o) : load4(ws + o);
+        const int j = j0 + acc_p(ib, g);
+        if (i < d && j < f) {
+          const int64_t o = (int64_t)i * f + j;
+          const f32x4 w = (c == 0) ? load4(W0 + o) : load4(ws + o);
           float nw[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) nw[e] = fmaf(-scale, acc[i][j][4 * g + e], w[e]);
+          for (int e = 0; e < 4; ++e) nw[e] = fmaf(-scale, acc[ib][jb][4 * g + e], w[e]);
           store4(ws + o, nw[0], nw[1], nw[2], nw[3]);
           if (wsh) store4(wsh + o, nw[0], nw[1], nw[2], nw[3]);
         }
       }
-    }
+  }
 }
 
 // ------------------------------------------------------------------ launchers
 
-static inline unsigned grid1(int64_t tiles) { return (unsigned)tiles; }
+static inline unsigned tiles_u(int64_t t) { return (unsigned)t; }
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <typename T>
-hipError_t launch_produce_z(const T* H, const T* Wg, const T* Wu, T* Z, int64_t rows, int d, int f, hipStream_t s) {
+hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  int64_t tiles = (int64_t)((f + 127) / 128) * ((rows + kTile - 1) / kTile);
-  k_produce_z<T><<<grid1(tiles), kThreads, 0, s>>>(H, Wg, Wu, Z, rows, d, f);
-  return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_produce_vhat(const T* X0, const T* cw, const T* Wt, T* Vh, int64_t rows, int n, int d, int K,
-                               hipStream_t s) {
-  if (rows == 0) return hipSuccess;
-  int64_t tiles = (int64_t)((d + kTile - 1) / kTile) * ((rows + kTile - 1) / kTile);
-  dim3 g(grid1(tiles));
+  const int64_t threads = cdiv(rows, 4) * (d / Vec<T>::V);
+  const dim3 g((unsigned)cdiv(threads, 256));
   switch (K) {
-#define TTT_KW(KW) case KW: k_produce_vhat<T, KW><<<g, kThreads, 0, s>>>(X0, cw, Wt, Vh, rows, n, d); break;
+#define TTT_KW(KW) case KW: k_conv<T, KW><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d); break;
     TTT_KW(1) TTT_KW(2) TTT_KW(3) TTT_KW(4) TTT_KW(5) TTT_KW(6) TTT_KW(7) TTT_KW(8)
 #undef TTT_KW
     default: return hipErrorInvalidValue;
@@ -447,10 +507,33 @@ hipError_t launch_produce_vhat(const T* X0, const T* cw, const T* Wt, T* Vh, int
 }
 
 template <typename T>
-hipError_t launch_chunk_delta(const T* Z, const T* Vh, float* dW, int B, int n, int d, int f, int C, hipStream_t s) {
-  int64_t tiles = (int64_t)((f + kTile - 1) / kTile) * ((d + kTile - 1) / kTile) * B * (n / C);
+hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int C, float scale, hipStream_t s) {
+  if (batch == 0 || R == 0 || C == 0) return hipSuccess;
+  k_transpose<T><<<dim3((unsigned)(cdiv(C, 64) * cdiv(R, 64)), (unsigned)batch), 256, 0, s>>>(src, dst, R, C, scale);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_produce_z(const T* H, const T* Wg, const T* Wu, T* Z, T* Zt, int64_t rows, int n, int d, int f,
+                            hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  k_produce_z<T><<<tiles_u(cdiv(rows, kTile) * cdiv(f, 128)), kThreads, 0, s>>>(H, Wg, Wu, Z, Zt, rows, n, d, f);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_produce_vhat(const T* Y, const T* WtT, T* Vt, int64_t rows, int n, int d, float scale,
+                               hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  k_produce_vhat<T><<<tiles_u(cdiv(rows, kTile) * cdiv(d, kTile)), kThreads, 0, s>>>(Y, WtT, Vt, rows, n, d, scale);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n, int d, int f, int C, hipStream_t s) {
+  const int64_t tiles = cdiv(f, kTile) * cdiv(d, kTile) * B * (n / C);
   if (tiles == 0) return hipSuccess;
-  k_chunk_delta<T><<<grid1(tiles), kThreads, 0, s>>>(Z, Vh, dW, B, n, d, f, C);
+  k_chunk_delta<T><<<tiles_u(tiles), kThreads, 0, s>>>(Zt, Vt, dW, n, d, f, C);
   return hipGetLastError();
 }
 
@@ -458,59 +541,60 @@ template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
                              hipStream_t s) {
   if (B == 0) return hipSuccess;
-  dim3 g((unsigned)((df / 4 + kThreads - 1) / kThreads), (unsigned)B);
-  k_chunk_scan<T><<<g, kThreads, 0, s>>>(dW, W0, Wc, Wf, k, df, eta);
+  k_chunk_scan<T><<<dim3((unsigned)cdiv(df / 4, kThreads), (unsigned)B), kThreads, 0, s>>>(dW, W0, Wc, Wf, k, df,
+                                                                                         eta);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_chunk_update_scan(const T* Z, const T* Vh, const T* W0, T* Wc, float* Wf, int B, int n, int d,
-                                    int f, int C, float eta, hipStream_t s) {
-  int64_t tiles = (int64_t)((f + kTile - 1) / kTile) * ((d + kTile - 1) / kTile) * B;
+hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, int B, int n, int d,
+                                    int f, int C, hipStream_t s) {
+  const int64_t tiles = cdiv(f, kTile) * cdiv(d, 128) * B;
   if (tiles == 0) return hipSuccess;
-  k_chunk_update_scan<T><<<grid1(tiles), kThreads, 0, s>>>(Z, Vh, W0, Wc, Wf, B, n, d, f, C, eta);
+  k_chunk_update_scan<T><<<tiles_u(tiles), kThreads, 0, s>>>(Zt, Vt, W0, Wc, Wf, n, d, f, C);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_apply(const T* Z, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
                         hipStream_t s) {
-  const int k = n / C;
-  int64_t tiles = (int64_t)((d + kTile - 1) / kTile) * ((C + kTile - 1) / kTile) * B * k;
+  const int64_t tiles = cdiv(d, kTile) * cdiv(C, kTile) * B * (n / C);
   if (tiles == 0) return hipSuccess;
-  k_apply<T, false><<<grid1(tiles), kThreads, 0, s>>>(Z, W, wsb, wsc, O, nullptr, nullptr, n, d, f, C, k, 0);
+  k_apply<T><<<tiles_u(tiles), kThreads, 0, s>>>(Z, W, wsb, wsc, O, n, d, f, C);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_mse_chunk(const T* Z, const T* Vh, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O, T* R, int B,
-                            int n, int d, int f, int C, int c, float eta, hipStream_t s) {
-  int64_t ta = (int64_t)((d + kTile - 1) / kTile) * ((C + kTile - 1) / kTile) * B;
+hipError_t launch_mse_chunk(const T* Z, const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
+                            T* Rt, int B, int n, int d, int f, int C, int c, float eta, hipStream_t s) {
   const int64_t df = (int64_t)d * f;
   // the state chunk c is applied with: W_down0 (shared) for c == 0, else this row's copy
   const T* W = (c == 0) ? W0 : Wcur;
   const int64_t wsb = (c == 0) ? 0 : df;
-  k_apply<T, true><<<grid1(ta), kThreads, 0, s>>>(Z, W, wsb, 0, O, Vh, R, n, d, f, C, 1, c);
+  k_mse_apply<T><<<tiles_u(cdiv(C, kTile) * cdiv(d, kTile) * B), kThreads, 0, s>>>(Z, W, wsb, O, Vt, Rt, n, d, f, C,
+                                                                                   c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t tu = (int64_t)((f + kTile - 1) / kTile) * ((d + kTile - 1) / kTile) * B;
-  k_mse_update<T><<<grid1(tu), kThreads, 0, s>>>(Z, R, W0, Ws, Wsh, n, d, f, C, c, eta / (float)C);
+  k_mse_update<T><<<tiles_u(cdiv(f, kTile) * cdiv(d, kTile) * B), kThreads, 0, s>>>(Zt, Rt, W0, Ws, Wsh, n, d, f, C,
+                                                                                   c, eta / (float)C);
   return hipGetLastError();
 }
 
 #define TTT_INST(T)                                                                                               \
-  template hipError_t launch_produce_z<T>(const T*, const T*, const T*, T*, int64_t, int, int, hipStream_t);     \
-  template hipError_t launch_produce_vhat<T>(const T*, const T*, const T*, T*, int64_t, int, int, int,            \
-                                             hipStream_t);                                                        \
+  template hipError_t launch_conv<T>(const T*, const T*, T*, int64_t, int, int, int, hipStream_t);                \
+  template hipError_t launch_transpose<T>(const T*, T*, int, int, int, float, hipStream_t);                      \
+  template hipError_t launch_produce_z<T>(const T*, const T*, const T*, T*, T*, int64_t, int, int, int,          \
+                                          hipStream_t);                                                           \
+  template hipError_t launch_produce_vhat<T>(const T*, const T*, T*, int64_t, int, int, float, hipStream_t);     \
   template hipError_t launch_chunk_delta<T>(const T*, const T*, float*, int, int, int, int, int, hipStream_t);   \
   template hipError_t launch_chunk_scan<T>(const float*, const T*, T*, float*, int, int, int64_t, float,         \
                                            hipStream_t);                                                          \
   template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, int, int, int, int,  \
-                                                  int, float, hipStream_t);                                       \
+                                                  int, hipStream_t);                                              \
   template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int,          \
                                       hipStream_t);                                                               \
-  template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*, int, int,  \
-                                          int, int, int, int, float, hipStream_t);
+  template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, const T*, float*, T*, T*, T*,   \
+                                          int, int, int, int, int, int, float, hipStream_t);
 TTT_INST(float)
 TTT_INST(bf16)
 #undef TTT_INST

@@ -9,24 +9,29 @@ namespace ttt {
 typedef __bf16 bf16;
 
 template <typename T>
-hipError_t launch_produce_z(const T* H, const T* Wg, const T* Wu, T* Z, int64_t rows, int d, int f, hipStream_t s);
+hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, hipStream_t s);
 template <typename T>
-hipError_t launch_produce_vhat(const T* X0, const T* cw, const T* Wt, T* Vh, int64_t rows, int n, int d, int K,
+hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int C, float scale, hipStream_t s);
+template <typename T>
+hipError_t launch_produce_z(const T* H, const T* Wg, const T* Wu, T* Z, T* Zt, int64_t rows, int n, int d, int f,
+                            hipStream_t s);
+template <typename T>
+hipError_t launch_produce_vhat(const T* Y, const T* WtT, T* Vt, int64_t rows, int n, int d, float scale,
                                hipStream_t s);
 template <typename T>
-hipError_t launch_chunk_delta(const T* Z, const T* Vh, float* dW, int B, int n, int d, int f, int C, hipStream_t s);
+hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n, int d, int f, int C, hipStream_t s);
 template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
                              hipStream_t s);
 template <typename T>
-hipError_t launch_chunk_update_scan(const T* Z, const T* Vh, const T* W0, T* Wc, float* Wf, int B, int n, int d,
-                                    int f, int C, float eta, hipStream_t s);
+hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, int B, int n, int d,
+                                    int f, int C, hipStream_t s);
 template <typename T>
 hipError_t launch_apply(const T* Z, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
                         hipStream_t s);
 template <typename T>
-hipError_t launch_mse_chunk(const T* Z, const T* Vh, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O, T* R, int B,
-                            int n, int d, int f, int C, int c, float eta, hipStream_t s);
+hipError_t launch_mse_chunk(const T* Z, const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
+                            T* Rt, int B, int n, int d, int f, int C, int c, float eta, hipStream_t s);
 
 // LaCT SwiGLU fast weight (one call runs every chunk of every (batch, head)).
 struct LactArgs {

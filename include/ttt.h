@@ -39,8 +39,8 @@
  *   - Each batch row is an independent document whose state starts at
  *     W_down0 (document-boundary reset, Method §3).
  *   - Supported sizes: d_model, d_ff and chunk multiples of 8, conv_k in
- *     1..8 (else TTT_ERR_UNSUPPORTED); seq_len a multiple of chunk (else
- *     TTT_ERR_SHAPE).  seq_len == 0 or batch == 0 is valid: no output rows,
+ *     1..8, seq_len <= 2^22 (else TTT_ERR_UNSUPPORTED); seq_len a multiple
+ *     of chunk (else TTT_ERR_SHAPE).  seq_len == 0 or batch == 0 is valid: no output rows,
  *     W_final rows (if any) equal W_down0.
  *   - The library keeps no global state; calls with distinct outputs and
  *     workspaces may run concurrently on different streams.
@@ -129,21 +129,31 @@ int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, f
                           void* stream);
 
 /* ---- the individual steps (each is one stage of the call above; they compose
- *      into it and exist for composition and per-step checks) ---- */
+ *      into it and exist for composition and per-step checks).  The updates
+ *      contract over tokens, so they read token-contiguous (transposed) copies:
+ *      Zt [B, f, n] and Vt [B, d, n]. ---- */
 
-/* Slow producer (eq. (2)): Z [B, n, f] = silu(H W_gate^T) * (H W_up^T).
- * conv_k and chunk of the shape are ignored (chunk must still be > 0). */
+/* Slow producer (eq. (2)): Z = silu(H W_gate^T) * (H W_up^T), written as
+ * Zt [B, f, n] (required) and Z [B, n, f] (may be NULL).  conv_k and chunk of
+ * the shape are not used (chunk must still divide seq_len). */
 int ttt_produce_z(const ttt_inplace_shape* shape, int dtype, const void* H, const void* W_gate,
-                  const void* W_up, void* Z, void* stream);
+                  const void* W_up, void* Z, void* Zt, void* stream);
+
+/* Workspace bytes for ttt_produce_vhat (the convolved embeddings and a
+ * transposed copy of W_target). */
+int ttt_vhat_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes);
 
 /* Target producer (eq. (5), causal padding of Method §3):
- * Vhat [B, n, d] = CausalDepthwiseConv1D_K(X0) W_target (conventions above). */
-int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, const void* X0, const void* conv_w,
-                     const void* W_target, void* Vhat, void* stream);
+ * Vt [B, d, n] = scale * (CausalDepthwiseConv1D_K(X0) W_target)^T (conventions
+ * above).  scale = 1 gives the target itself; scale = eta gives the form the
+ * fused update takes. */
+int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, float scale, const void* X0, const void* conv_w,
+                     const void* W_target, void* Vt, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-chunk deltas of the dot objective (Method §3 step 1, eq. (6)):
- * dW [B, k, d, f] fp32, dW[b, c] = Vhat_c^T Z_c over the chunk's C tokens. */
-int ttt_chunk_delta(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Vhat,
+ * dW [B, k, d, f] fp32, dW[b, c] = Vhat_c^T Z_c over the chunk's C tokens,
+ * read from Zt [B, f, n] and Vt [B, d, n]. */
+int ttt_chunk_delta(const ttt_inplace_shape* shape, int dtype, const void* Zt, const void* Vt,
                     float* dW, void* stream);
 
 /* Exclusive prefix scan over chunks (Method §3 steps 2-3):
@@ -153,14 +163,18 @@ int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const v
                    const float* dW, void* Wc, float* W_final, void* stream);
 
 /* Deltas and scan fused (chunk % 64 == 0 for bf16, % 32 for fp32, else
- * TTT_ERR_UNSUPPORTED): one MFMA pass over the sequence per output tile whose
- * fp32 accumulator is the running prefix; at each chunk boundary the tile
- * writes Wc[b, c] = W_down0 + eta * accumulator.  Same outputs as
- * ttt_chunk_delta followed by ttt_chunk_scan, without dW. */
-int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, float eta, const void* W_down0,
-                          const void* Z, const void* Vhat, void* Wc, float* W_final, void* stream);
+ * TTT_ERR_UNSUPPORTED), with eta carried by the target: Vt = eta * V^^T (from
+ * ttt_produce_vhat with scale = eta), since eta V^_c^T Z_c = (eta V^_c)^T Z_c.
+ * One MFMA pass over the sequence per output tile, whose fp32 accumulator
+ * starts at W_down0 and so holds W_c after the tokens of chunks 0..c-1; at
+ * each chunk boundary the tile writes Wc[b, c], after the last chunk W_final.
+ * Same outputs as ttt_chunk_delta (on the unscaled target) followed by
+ * ttt_chunk_scan with eta, without dW. */
+int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void* W_down0,
+                          const void* Zt, const void* Vt, void* Wc, float* W_final, void* stream);
 
-/* Apply (eq. (3)): O [B, n, d], O_c = Z_c Wc[b, c]^T with Wc [B, k, d, f] dtype. */
+/* Apply (eq. (3)): O [B, n, d], O_c = Z_c Wc[b, c]^T with Z [B, n, f] and
+ * Wc [B, k, d, f] dtype. */
 int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Wc, void* O,
                     void* stream);
 

@@ -48,18 +48,24 @@ def test_workspace_sizes():
     B, n, d, f, C = 1, 2048, 256, 512, 256
     k = n // C
     al = lambda x: (x + 255) // 256 * 256
+    core = lambda e, B=B: al(B * n * f * e) + al(B * n * d * e)          # Zt, Vt
+    prod = lambda e: al(B * n * f * e) + al(B * n * d * e) + al(d * d * e)   # Z, conv output, W_target^T
     st, nb = _ws(_shape(), cw.TTT_F32, cw.TTT_MODE_DOT, 1)
     assert st == cw.TTT_OK
-    assert nb == al(B * n * f * 4) + al(B * n * d * 4) + al(B * k * d * f * 4)
+    assert nb == prod(4) + core(4) + al(B * k * d * f * 4)
     st, nb = _ws(_shape(), cw.TTT_BF16, cw.TTT_MODE_DOT_SCAN, 0)
-    assert st == cw.TTT_OK and nb == al(B * k * d * f * 2) + al(B * k * d * f * 4)
+    assert st == cw.TTT_OK and nb == core(2) + al(B * k * d * f * 2) + al(B * k * d * f * 4)
     st, nb = _ws(_shape(B=4), cw.TTT_BF16, cw.TTT_MODE_MSE, 0)
-    assert st == cw.TTT_OK and nb == al(4 * C * d * 2) + al(4 * d * f * 2)
+    assert st == cw.TTT_OK and nb == core(2, 4) + al(4 * C * d * 2) + al(4 * d * f * 2)
     st, nb = _ws(_shape(B=4), cw.TTT_F32, cw.TTT_MODE_MSE, 0)
-    assert st == cw.TTT_OK and nb == al(4 * C * d * 4)
+    assert st == cw.TTT_OK and nb == core(4, 4) + al(4 * C * d * 4)
     # chunk not a multiple of the 64-element K step: dot falls back to the materialised scan
-    st, nb = _ws(_shape(n=2000, C=40), cw.TTT_BF16, cw.TTT_MODE_DOT, 0)
-    assert st == cw.TTT_OK and nb == al(50 * d * f * 2) + al(50 * d * f * 4)
+    n2 = 2000
+    st, nb = _ws(_shape(n=n2, C=40), cw.TTT_BF16, cw.TTT_MODE_DOT, 0)
+    assert st == cw.TTT_OK and nb == al(n2 * f * 2) + al(n2 * d * 2) + al(50 * d * f * 2) + al(50 * d * f * 4)
+    out = ctypes.c_size_t(0)
+    assert cw.lib().ttt_vhat_workspace_bytes(ctypes.byref(_shape()), cw.TTT_BF16, ctypes.byref(out)) == cw.TTT_OK
+    assert out.value == al(n * d * 2) + al(d * d * 2)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -118,13 +124,18 @@ def test_call_rejects_null_and_misaligned_pointers_before_device_work():
 def test_step_entry_points_validate():
     lib = cw.lib()
     s = _shape()
-    assert lib.ttt_produce_z(ctypes.byref(s), cw.TTT_BF16, None, _fake(), _fake(), _fake(), None) == cw.TTT_ERR_ARG
-    assert lib.ttt_produce_vhat(ctypes.byref(_shape(K=9)), cw.TTT_BF16, *[_fake()] * 4, None) == \
+    assert lib.ttt_produce_z(ctypes.byref(s), cw.TTT_BF16, None, _fake(), _fake(), _fake(), _fake(), None) == \
+        cw.TTT_ERR_ARG
+    assert lib.ttt_produce_z(ctypes.byref(s), cw.TTT_BF16, _fake(), _fake(), _fake(), _fake(), None, None) == \
+        cw.TTT_ERR_ARG                                                      # Zt is required
+    assert lib.ttt_produce_vhat(ctypes.byref(_shape(K=9)), cw.TTT_BF16, 1.0, *[_fake()] * 5, 1 << 30, None) == \
         cw.TTT_ERR_UNSUPPORTED
+    assert lib.ttt_produce_vhat(ctypes.byref(s), cw.TTT_BF16, 1.0, *[_fake()] * 5, 16, None) == \
+        cw.TTT_ERR_WORKSPACE
     assert lib.ttt_chunk_delta(ctypes.byref(_shape(n=100)), cw.TTT_BF16, *[_fake()] * 3, None) == cw.TTT_ERR_SHAPE
     assert lib.ttt_chunk_scan(ctypes.byref(s), cw.TTT_BF16, float("inf"), *[_fake()] * 4, None) == cw.TTT_ERR_ARG
     # the fused update-scan needs chunk boundaries on 64-token steps in bf16
-    assert lib.ttt_chunk_update_scan(ctypes.byref(_shape(n=2048, C=32)), cw.TTT_BF16, 0.1, *[_fake()] * 5, None) == \
+    assert lib.ttt_chunk_update_scan(ctypes.byref(_shape(n=2048, C=32)), cw.TTT_BF16, *[_fake()] * 5, None) == \
         cw.TTT_ERR_UNSUPPORTED
     assert lib.ttt_chunk_apply(ctypes.byref(s), cw.TTT_BF16, _fake(), None, _fake(), None) == cw.TTT_ERR_ARG
 

@@ -47,11 +47,15 @@ def test_produce_z(dtype):
     cfg = small_cfg(dtype, "dot", B=2, n=520, d=264, f=392)
     x = ti.inplace_inputs(cfg)
     g = dev(x)
-    Z = cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"])
+    Z, Zt = cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"])
     torch.cuda.synchronize()
     ref = orc.gated_intermediate(ti.to_f64(x["H"]).reshape(-1, cfg.d_model), ti.to_f64(x["W_gate"]),
                                  ti.to_f64(x["W_up"])).reshape(2, 520, 392)
     assert rel(f64(Z), ref) < STEP_TOL[dtype]
+    assert torch.equal(Zt, Z.transpose(1, 2).contiguous())      # the two layouts hold the same values
+    _, Zt_only = cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"], with_z=False)
+    torch.cuda.synchronize()
+    assert torch.equal(Zt_only, Zt)
 
 
 @pytest.mark.parametrize("dtype,K", [("f32", 4), ("bf16", 4), ("bf16", 1), ("bf16", 3), ("f32", 8)])
@@ -59,10 +63,12 @@ def test_produce_vhat(dtype, K):
     cfg = small_cfg(dtype, "dot", B=2, n=384, d=328, f=64, K=K)
     x = ti.inplace_inputs(cfg)
     g = dev(x)
-    V = cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"])
+    Vt = cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"])
+    Vt_s = cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"], scale=0.25)
     torch.cuda.synchronize()
     ref = orc.target_values(ti.to_f64(x["X0"]), ti.to_f64(x["conv_w"]), ti.to_f64(x["W_target"]))
-    assert rel(f64(V), ref) < STEP_TOL[dtype]
+    assert rel(f64(Vt), ref.transpose(0, 2, 1)) < STEP_TOL[dtype]
+    assert rel(f64(Vt_s), 0.25 * ref.transpose(0, 2, 1)) < STEP_TOL[dtype]
 
 
 def _zv(dtype, B, n, d, f, seed):
@@ -74,12 +80,16 @@ def _zv(dtype, B, n, d, f, seed):
     return Z, V, W0
 
 
+def _t(x):
+    return x.transpose(1, 2).contiguous()
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_delta_scan_apply_steps(dtype):
     B, n, d, f, C, eta = 2, 768, 264, 392, 192, 0.02
     Z, V, W0 = _zv(dtype, B, n, d, f, 11)
-    Zg, Vg, Wg = Z.cuda(), V.cuda(), W0.cuda()
-    dW = cw.ttt_chunk_delta(Zg, Vg, C)
+    Zg, Wg = Z.cuda(), W0.cuda()
+    dW = cw.ttt_chunk_delta(_t(Z).cuda(), _t(V).cuda(), C)
     Wc, Wf = cw.ttt_chunk_scan(dW, Wg, eta, C, n)
     O = cw.ttt_chunk_apply(Zg, Wc, C)
     torch.cuda.synchronize()
@@ -100,16 +110,19 @@ def test_delta_scan_apply_steps(dtype):
 def test_fused_update_scan_matches_materialised(dtype):
     B, n, d, f, C, eta = 2, 1024, 264, 520, 256, 0.02
     Z, V, W0 = _zv(dtype, B, n, d, f, 12)
-    Zg, Vg, Wg = Z.cuda(), V.cuda(), W0.cuda()
-    Wc1, Wf1 = cw.ttt_chunk_update_scan(Zg, Vg, Wg, C, eta)
-    Wc2, Wf2 = cw.ttt_chunk_scan(cw.ttt_chunk_delta(Zg, Vg, C), Wg, eta, C, n)
+    dt = Z.dtype
+    Vs = (V.double() * eta).to(dt)                # the eta-scaled target the fused update takes
+    Zt, Wg = _t(Z).cuda(), W0.cuda()
+    Wc1, Wf1 = cw.ttt_chunk_update_scan(Zt, _t(Vs).cuda(), Wg, C)
+    Wc2, Wf2 = cw.ttt_chunk_scan(cw.ttt_chunk_delta(Zt, _t(V).cuda(), C), Wg, eta, C, n)
     torch.cuda.synchronize()
-    Zn, Vn, W0n = f64(Z), f64(V), f64(W0)
+    Zn, Vsn, W0n = f64(Z), f64(Vs), f64(W0)
     for b in range(B):
-        _, Wref = orc.chunk_prefix_form(Zn[b], Vn[b], W0n, C, eta)
+        _, Wref = orc.chunk_prefix_form(Zn[b], Vsn[b], W0n, C, 1.0)
         assert rel(f64(Wf1[b]), Wref) < 1e-5
         assert rel(f64(Wf1[b]) - W0n, Wref - W0n) < 1e-5
     assert rel(f64(Wc1), f64(Wc2)) < STEP_TOL[dtype]
+    assert rel(f64(Wf1), f64(Wf2)) < STEP_TOL[dtype]
     assert torch.equal(Wc1[:, 0], Wg.expand(B, d, f))      # chunk 0 is applied with W_down0
 
 
@@ -182,14 +195,17 @@ def test_step_composition_equals_full_call():
     g = dev(x)
     O, Wf = cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"],
                                       g["conv_w"], cfg.chunk, cfg.eta, "dot")
-    Z = cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"])
-    V = cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"])
-    Wc, Wf2 = cw.ttt_chunk_update_scan(Z, V, g["W_down0"], cfg.chunk, cfg.eta)
+    Z, Zt = cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"])
+    Vt = cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"], scale=cfg.eta)
+    Wc, Wf2 = cw.ttt_chunk_update_scan(Zt, Vt, g["W_down0"], cfg.chunk)
     O2 = cw.ttt_chunk_apply(Z, Wc, cfg.chunk)
-    O3, Wf3 = cw.ttt_core_apply_update(Z, V, g["W_down0"], cfg.chunk, cfg.eta, "dot")
     torch.cuda.synchronize()
     assert torch.equal(O, O2) and torch.equal(Wf, Wf2)
-    assert torch.equal(O, O3) and torch.equal(Wf, Wf3)
+    # the chunk loop alone, from Z and V^ in their natural layouts
+    V = cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"]).transpose(1, 2).contiguous()
+    O3, Wf3 = cw.ttt_core_apply_update(Z, V, g["W_down0"], cfg.chunk, cfg.eta, "dot")
+    torch.cuda.synchronize()
+    assert rel(f64(O3), f64(O)) < STEP_TOL["bf16"] and rel(f64(Wf3), f64(Wf)) < STEP_TOL["bf16"]
 
 
 # ---------------------------------------------------------------- invariants
