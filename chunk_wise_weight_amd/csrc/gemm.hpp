@@ -1,22 +1,27 @@
 // MFMA tile engine for gfx950 (CDNA4), shared by every contraction of the layer.
 //
-// A workgroup of 256 threads (4 waves of 64) owns a 256 x BQ tile (BQ = 256
-// or 128) acc[p][q] = sum_k P[p][k] * Q[q][k] and walks K in steps of 128
-// bytes (64 bf16 or 32 fp32).  Both operands are K-contiguous in global
-// memory.  Each wave owns a 128 x BQ/2 quarter: 4 x NQB 32x32 MFMA accumulator
-// blocks (NQB = BQ / 64), 64 NQB fp32 per lane, allocated to AGPRs.
+// A workgroup of NW = WP x WQ waves owns a BP x BQ tile acc[p][q] =
+// sum_k P[p][k] * Q[q][k] and walks K in steps of 128 bytes (64 bf16 or 32
+// fp32).  Both operands are K-contiguous in global memory.  Wave (wp, wq)
+// owns NPB x NQB 32x32 MFMA accumulator blocks (BP = 32 NPB WP,
+// BQ = 32 NQB WQ).  Two shapes are used:
+//   Wide   = 8 waves, 2 x 4, 4 x 2 blocks: 256 x 256 tile, 128 accumulators
+//            per lane, two waves per SIMD so that one wave's LDS and barrier
+//            waits are covered by the other's MFMAs;
+//   Narrow = 4 waves, 2 x 2, 4 x 2 blocks: 256 x 128 tile, for grids where a
+//            256 x 256 tiling would leave most of a wave of workgroups idle.
 //
 // Global -> LDS: buffer_load_dwordx4 ... lds (LDS DMA).  One instruction moves
 // 64 lanes x 16 B = 8 rows x 128 B of a tile with no VGPR staging.  Out-of-range
 // rows and the K tail are read through a per-lane offset past the buffer
 // resource's range, which the hardware returns as zero: no branches.
 //
-// LDS layout of a tile: 256 rows of 128 B; the 16-byte chunk c of row r sits
-// in slot c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows hit
-// 8 different bank groups.  The DMA reaches this layout by letting lane L of an
+// LDS layout of a tile: rows of 128 B; the 16-byte chunk c of row r sits in
+// slot c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows hit 8
+// different bank groups.  The DMA reaches this layout by letting lane L of an
 // instruction fetch chunk (L & 7) ^ (L >> 3) of its row.  Two stages of
-// (256 + 256) x 128 B = 128 KB: step k+1 is in flight while step k is
-// multiplied; one barrier per step (LDS: 2 x (256 + BQ) x 128 B).
+// (BP + BQ) x 128 B: step k+1 is in flight while step k is multiplied; one
+// barrier per step.
 //
 // MFMA mapping (v_mfma_f32_32x32x16_bf16, or 4 x v_mfma_f32_32x32x2_f32 for
 // fp32): P feeds the instruction's A slot, Q its B slot.  A lane therefore
@@ -28,28 +33,37 @@
 
 namespace ttt {
 
-// GEMM kernels hold 256 accumulators per lane in AGPRs, which caps occupancy at
-// one wave per SIMD anyway; saying so lets the scheduler spend registers on
-// keeping LDS fragment reads ahead of the MFMAs instead of minimising them.
-#define TTT_ONE_WAVE __attribute__((amdgpu_waves_per_eu(1, 1)))
-
-constexpr int kThreads = 256;
-constexpr int kTile = 256;                  // rows of the P tile
-constexpr int kTileBytes = kTile * 128;     // bytes of one P tile stage
-constexpr int kSmemBytes = 2 * (kTile + kTile) * 128;   // enough for either tile shape
-
-// Stage layout for a 256 x BQ tile: P tile then Q tile.
-template <int NQB> struct TileShape {
-  static constexpr int BQ = 64 * NQB;
-  static constexpr int kQBytes = BQ * 128;
-  static constexpr int kStage = kTileBytes + kQBytes;
-  static constexpr int kSmem = 2 * kStage;
-};
 constexpr unsigned kOOB = 0x80000000u;     // any offset >= this is outside every resource
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+template <int WP_, int WQ_, int NPB_, int NQB_>
+struct TileCfg {
+  static constexpr int WP = WP_, WQ = WQ_, NPB = NPB_, NQB = NQB_;
+  static constexpr int NW = WP * WQ, NT = 64 * NW;
+  static constexpr int BP = 32 * NPB * WP, BQ = 32 * NQB * WQ;
+  static constexpr int PBytes = BP * 128, QBytes = BQ * 128;
+  static constexpr int Stage = PBytes + QBytes, Smem = 2 * Stage;
+  // tile coordinates of this lane's accumulators: block (i, j), register
+  // group g covers p = acc_p(i, g) + 0..3 at q = acc_q(j)
+  __device__ static __forceinline__ int acc_p(int i, int g) {
+    return (wave_id() / WQ) * (32 * NPB) + i * 32 + g * 8 + (lane_id() >> 5) * 4;
+  }
+  __device__ static __forceinline__ int acc_q(int j) { return (wave_id() % WQ) * (32 * NQB) + j * 32 + (lane_id() & 31); }
+};
+using Wide = TileCfg<2, 4, 4, 2>;
+using Narrow = TileCfg<2, 2, 4, 2>;
+
+// Kernel attributes: NT threads, and the number of waves per SIMD the register
+// budget is planned for (the scheduler then spends registers on keeping LDS
+// fragment reads ahead of the MFMAs).
+#define TTT_GEMM_KERNEL(C) \
+  __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::NW / 4, C::NW / 4)))
 
 // ---------------------------------------------------------------- tile scheduling
 
@@ -80,49 +94,45 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
 }
 
-// Byte offset, inside a 128-byte row, of the chunk this lane fetches.
-__device__ __forceinline__ unsigned dma_chunk_bytes() {
-  const unsigned L = threadIdx.x & 63u;
-  return ((L & 7u) ^ (L >> 3)) << 4;
-}
-
-// K-contiguous operand moved by DMA into a ROWS-row tile.  Plain: instruction
-// i of wave w fills tile rows (ROWS/4) w + 8 i + (0..7) from consecutive rows of
-// one matrix.  DUAL (ROWS = 256): rows come in 32-row blocks alternating between
-// two matrices (instructions 0..3 read the first, 4..7 the second), block pair
-// w holding rows 32 w + (0..31) of both.
-template <bool DUAL, int ROWS = 256>
+// K-contiguous operand moved by DMA into a ROWS-row tile by NW waves: DMA
+// instruction i of wave w fills tile rows 8 (NI w + i) + (0..7), NI = ROWS /
+// (8 NW).  Plain: tile row r is matrix row r.  DUAL: tile rows come in 32-row
+// blocks alternating between two matrices (even blocks from the first, odd
+// from the second), block 2m + s holding rows 32 m + (0..31) of matrix s.
+template <int NW, int ROWS, bool DUAL = false>
 struct DmaOp {
-  static constexpr int NI = ROWS / 32;      // DMA instructions per wave
-  static_assert(!DUAL || ROWS == 256, "dual operands fill 256-row tiles");
+  static constexpr int NI = ROWS / (8 * NW);
+  static_assert(NI >= 1 && NI * 8 * NW == ROWS, "tile rows must split evenly over the waves");
   __amdgpu_buffer_rsrc_t rs0, rs1;
-  unsigned off[DUAL ? 4 : NI];
+  unsigned off[NI];
   unsigned kbytes;
 
-  // rows_valid: rows of this tile inside the matrix; ld_bytes: row pitch.
+  // rows_valid: rows of each source matrix inside this tile; ld_bytes: row pitch.
   __device__ __forceinline__ void init(const void* base0, const void* base1, int rows_valid, uint64_t ld_bytes,
                                        unsigned kbytes_) {
     kbytes = kbytes_;
-    const int w = threadIdx.x >> 6, L = threadIdx.x & 63;
+    const int w = wave_id(), L = lane_id();
     const uint64_t span = rows_valid > 0 ? (uint64_t)(rows_valid - 1) * ld_bytes + kbytes_ : 0;
     rs0 = make_rsrc(base0, span);
     rs1 = make_rsrc(DUAL ? base1 : base0, span);
 #pragma unroll
-    for (int i = 0; i < (DUAL ? 4 : NI); ++i) {
-      const int r = DUAL ? w * 32 + i * 8 + (L >> 3) : w * (ROWS / 4) + i * 8 + (L >> 3);
-      off[i] = r < rows_valid ? (unsigned)(r * ld_bytes) : kOOB;
+    for (int i = 0; i < NI; ++i) {
+      const int r = (w * NI + i) * 8 + (L >> 3);
+      const int mr = DUAL ? ((r >> 6) << 5) + (r & 31) : r;
+      off[i] = mr < rows_valid ? (unsigned)(mr * ld_bytes) : kOOB;
     }
   }
   __device__ __forceinline__ void issue(int ks, char* tile) const {
-    const unsigned kb = (unsigned)ks * 128u + dma_chunk_bytes();
+    const unsigned L = lane_id();
+    const unsigned kb = (unsigned)ks * 128u + (((L & 7u) ^ (L >> 3)) << 4);
     const bool kin = kb < kbytes;
-    char* base = tile + (threadIdx.x >> 6) * NI * 1024;
+    const int w = wave_id();
+    char* base = tile + w * NI * 1024;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const unsigned o = DUAL ? off[i & 3] : off[i];
-      const unsigned voff = kin ? o + kb : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds((DUAL && i >= 4) ? rs1 : rs0, (lds_ptr_t)(base + i * 1024), 16, voff,
-                                               0, 0, 0);
+      const bool second = DUAL && ((((w * NI + i) * 8) >> 5) & 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rs1 : rs0, (lds_ptr_t)(base + i * 1024), 16,
+                                               kin ? off[i] + kb : kOOB, 0, 0, 0);
     }
   }
 };
@@ -143,87 +153,78 @@ __device__ __forceinline__ void mma(f32x16& acc, u32x4 p, u32x4 q, float*) {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(p[e]), __uint_as_float(q[e]), acc, 0, 0, 0);
 }
 
-template <int NQB>
-__device__ __forceinline__ void load_frags(const char* tp, const char* tq, int g, u32x4 (&pf)[4], u32x4 (&qf)[NQB]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int prow = (w >> 1) * 128 + (lane & 31);
-  const int qrow = (w & 1) * (32 * NQB) + (lane & 31);
+template <class C, class PF, class QF>
+__device__ __forceinline__ void load_frags(const char* tp, const char* tq, int g, PF& pf, QF& qf) {
+  const int lane = lane_id(), w = wave_id();
+  const int prow = (w / C::WQ) * (32 * C::NPB) + (lane & 31);
+  const int qrow = (w % C::WQ) * (32 * C::NQB) + (lane & 31);
   const int chunk = 2 * g + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) pf[i] = *reinterpret_cast<const u32x4*>(tp + lds_off(prow + 32 * i, chunk));
+  for (int i = 0; i < C::NPB; ++i) pf[i] = *reinterpret_cast<const u32x4*>(tp + lds_off(prow + 32 * i, chunk));
 #pragma unroll
-  for (int j = 0; j < NQB; ++j) qf[j] = *reinterpret_cast<const u32x4*>(tq + lds_off(qrow + 32 * j, chunk));
+  for (int j = 0; j < C::NQB; ++j) qf[j] = *reinterpret_cast<const u32x4*>(tq + lds_off(qrow + 32 * j, chunk));
 }
 
 // One K step (four groups of 16 k for bf16 / 8 k for fp32).  Fragments are
 // double-buffered in registers: the LDS reads of group g + 1 are issued before
 // the MFMAs of group g, and scheduling fences keep the compiler from sinking
 // them back next to their use.
-template <typename T, int NQB>
-__device__ __forceinline__ void compute_stage(const char* tp, const char* tq, f32x16 (&acc)[4][NQB]) {
-  u32x4 pf[2][4], qf[2][NQB];
-  load_frags<NQB>(tp, tq, 0, pf[0], qf[0]);
+template <typename T, class C, class Acc>
+__device__ __forceinline__ void compute_stage(const char* tp, const char* tq, Acc& acc) {
+  u32x4 pf[2][C::NPB], qf[2][C::NQB];
+  load_frags<C>(tp, tq, 0, pf[0], qf[0]);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const int cur = g & 1;
-    if (g < 3) load_frags<NQB>(tp, tq, g + 1, pf[cur ^ 1], qf[cur ^ 1]);
+    if (g < 3) load_frags<C>(tp, tq, g + 1, pf[cur ^ 1], qf[cur ^ 1]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < C::NPB; ++i)
 #pragma unroll
-      for (int j = 0; j < NQB; ++j) mma(acc[i][j], pf[cur][i], qf[cur][j], (T*)nullptr);
+      for (int j = 0; j < C::NQB; ++j) mma(acc[i][j], pf[cur][i], qf[cur][j], (T*)nullptr);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 struct NoHook {
-  template <int NQB>
-  __device__ __forceinline__ void operator()(int, f32x16 (&)[4][NQB]) const {}
+  template <class A>
+  __device__ __forceinline__ void operator()(int, A&) const {}
 };
 
-template <int NQB>
-__device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][NQB]) {
+template <class C, class Acc>
+__device__ __forceinline__ void zero_acc(Acc& acc) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < C::NPB; ++i)
 #pragma unroll
-    for (int j = 0; j < NQB; ++j) acc[i][j] = (f32x16){};
+    for (int j = 0; j < C::NQB; ++j) acc[i][j] = (f32x16){};
 }
 
 // nks steps over K.  hook(ks, acc) runs after step ks, past the barrier; it
 // may read and write global memory but not LDS.
-template <typename T, int NQB, class OP, class OQ, class Hook>
-__device__ __forceinline__ void mainloop(const OP& op, const OQ& oq, int nks, f32x16 (&acc)[4][NQB], char* smem,
+template <typename T, class C, class OP, class OQ, class Hook, class Acc>
+__device__ __forceinline__ void mainloop(const OP& op, const OQ& oq, int nks, Acc& acc, char* smem,
                                          const Hook& hook) {
-  using S = TileShape<NQB>;
+  // The host compilation pass only needs the kernels' signatures; instantiating
+  // this body there (target builtins, inline asm) trips template deduction.
+#if defined(__HIP_DEVICE_COMPILE__)
   if (nks <= 0) return;
   op.issue(0, smem);
-  oq.issue(0, smem + kTileBytes);
+  oq.issue(0, smem + C::PBytes);
   wait_dma();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
-    char* cur = smem + (ks & 1) * S::kStage;
-    char* nxt = smem + ((ks & 1) ^ 1) * S::kStage;
+    char* cur = smem + (ks & 1) * C::Stage;
+    char* nxt = smem + ((ks & 1) ^ 1) * C::Stage;
     if (ks + 1 < nks) {
       op.issue(ks + 1, nxt);
-      oq.issue(ks + 1, nxt + kTileBytes);
+      oq.issue(ks + 1, nxt + C::PBytes);
     }
-    compute_stage<T, NQB>(cur, cur + kTileBytes, acc);
+    compute_stage<T, C>(cur, cur + C::PBytes, acc);
     wait_dma();
     __syncthreads();
     hook(ks, acc);
   }
-}
-
-// Coordinates of this lane's accumulator values inside the tile: block (i, j),
-// register group g covers p = acc_p(i, g) + 0..3 at q = acc_q(j).
-__device__ __forceinline__ int acc_p(int i, int g) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  return (w >> 1) * 128 + i * 32 + g * 8 + (lane >> 5) * 4;
-}
-template <int NQB = 4>
-__device__ __forceinline__ int acc_q(int j) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  return (w & 1) * (32 * NQB) + j * 32 + (lane & 31);
+#endif
 }
 
 }  // namespace ttt

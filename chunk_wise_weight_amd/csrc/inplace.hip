@@ -105,48 +105,45 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, T*
 
 // Z = silu(H W_gate^T) * (H W_up^T)  (eq. (2)).  P = tokens, Q = gate and up
 // rows in alternating 32-row blocks, so a lane holds the gate and the up value
-// of one output column in Q blocks jj and jj + 1, for 4 consecutive tokens.
+// of one output column in Q blocks 0 and 1, for 4 consecutive tokens.
 // Writes Zt[b, j, t..t+3] (packed) and, if Z is given, Z[t + e, j].
 template <typename T>
-__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_produce_z(const T* __restrict__ H, const T* __restrict__ Wg,
-                                                         const T* __restrict__ Wu, T* __restrict__ Z,
-                                                         T* __restrict__ Zt, int64_t rows, int n, int d, int f) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int TP = (int)((rows + kTile - 1) / kTile), TQ = (f + 127) / 128;
+TTT_GEMM_KERNEL(Wide) void k_produce_z(const T* __restrict__ H, const T* __restrict__ Wg, const T* __restrict__ Wu,
+                                       T* __restrict__ Z, T* __restrict__ Zt, int64_t rows, int n, int d, int f) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (int)((rows + G::BP - 1) / G::BP), TQ = (f + G::BQ / 2 - 1) / (G::BQ / 2);
   int tp, tq;
   grouped_tile(xcd_remap(blockIdx.x, gridDim.x), TP, TQ, 4, tp, tq);
-  const int64_t t0 = (int64_t)tp * kTile;
-  const int j0 = tq * 128;
+  const int64_t t0 = (int64_t)tp * G::BP;
+  const int j0 = tq * (G::BQ / 2);
   const uint64_t ldb = (uint64_t)d * esz<T>();
 
-  DmaOp<false> op;
-  op.init(H + t0 * d, nullptr, (int)min<int64_t>(kTile, rows - t0), ldb, (unsigned)ldb);
-  DmaOp<true> oq;
-  oq.init(Wg + (int64_t)j0 * d, Wu + (int64_t)j0 * d, min(128, f - j0), ldb, (unsigned)ldb);
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  mainloop<T>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
+  DmaOp<G::NW, G::BP> op;
+  op.init(H + t0 * d, nullptr, (int)min<int64_t>(G::BP, rows - t0), ldb, (unsigned)ldb);
+  DmaOp<G::NW, G::BQ, true> oq;
+  oq.init(Wg + (int64_t)j0 * d, Wu + (int64_t)j0 * d, min(G::BQ / 2, f - j0), ldb, (unsigned)ldb);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  static_assert(G::NQB == 2, "one gate/up block pair per wave");
+  const int j = j0 + (wave_id() % G::WQ) * 32 + (lane_id() & 31);
+  if (j >= f) return;
 #pragma unroll
-  for (int jj = 0; jj < 4; jj += 2) {
-    const int j = j0 + ((w & 1) * 2 + (jj >> 1)) * 32 + (lane & 31);
-    if (j >= f) continue;
+  for (int i = 0; i < G::NPB; ++i) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int g = 0; g < 4; ++g) {
+      const int64_t row = t0 + G::acc_p(i, g);
+      if (row >= rows) continue;
+      float z[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t row = t0 + acc_p(i, g);
-        if (row >= rows) continue;
-        float z[4];
+      for (int e = 0; e < 4; ++e) z[e] = silu_f(acc[i][0][4 * g + e]) * acc[i][1][4 * g + e];
+      const int64_t b = row / n, t = row - b * n;
+      store4(Zt + (b * f + j) * (int64_t)n + t, z[0], z[1], z[2], z[3]);
+      if (Z != nullptr) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = silu_f(acc[i][jj][4 * g + e]) * acc[i][jj + 1][4 * g + e];
-        const int64_t b = row / n, t = row - b * n;
-        store4(Zt + (b * f + j) * (int64_t)n + t, z[0], z[1], z[2], z[3]);
-        if (Z != nullptr) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Z[(row + e) * f + j] = from_f32<T>(z[e]);
-        }
+        for (int e = 0; e < 4; ++e) Z[(row + e) * f + j] = from_f32<T>(z[e]);
       }
     }
   }
@@ -155,33 +152,34 @@ __global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_produce_z(const T* __
 // Vt = scale * (Y W_target)^T with WtT = W_target^T [d_out, d_in].  P = tokens,
 // Q = output channels; writes Vt[b, o, t..t+3].
 template <typename T>
-__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_produce_vhat(const T* __restrict__ Y, const T* __restrict__ WtT,
-                                                            T* __restrict__ Vt, int64_t rows, int n, int d,
-                                                            float scale) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int TP = (int)((rows + kTile - 1) / kTile), TQ = (d + kTile - 1) / kTile;
+TTT_GEMM_KERNEL(Wide) void k_produce_vhat(const T* __restrict__ Y, const T* __restrict__ WtT, T* __restrict__ Vt,
+                                          int64_t rows, int n, int d, float scale) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (int)((rows + G::BP - 1) / G::BP), TQ = (d + G::BQ - 1) / G::BQ;
   int tp, tq;
   grouped_tile(xcd_remap(blockIdx.x, gridDim.x), TP, TQ, 4, tp, tq);
-  const int64_t t0 = (int64_t)tp * kTile;
-  const int o0 = tq * kTile;
+  const int64_t t0 = (int64_t)tp * G::BP;
+  const int o0 = tq * G::BQ;
   const uint64_t ldb = (uint64_t)d * esz<T>();
 
-  DmaOp<false> op, oq;
-  op.init(Y + t0 * d, nullptr, (int)min<int64_t>(kTile, rows - t0), ldb, (unsigned)ldb);
-  oq.init(WtT + (int64_t)o0 * d, nullptr, min(kTile, d - o0), ldb, (unsigned)ldb);
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  mainloop<T>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
+  DmaOp<G::NW, G::BP> op;
+  DmaOp<G::NW, G::BQ> oq;
+  op.init(Y + t0 * d, nullptr, (int)min<int64_t>(G::BP, rows - t0), ldb, (unsigned)ldb);
+  oq.init(WtT + (int64_t)o0 * d, nullptr, min(G::BQ, d - o0), ldb, (unsigned)ldb);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int o = o0 + acc_q(j);
+  for (int j = 0; j < G::NQB; ++j) {
+    const int o = o0 + G::acc_q(j);
     if (o >= d) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int64_t row = t0 + acc_p(i, g);
+        const int64_t row = t0 + G::acc_p(i, g);
         if (row >= rows) continue;
         const int64_t b = row / n, t = row - b * n;
         store4(Vt + (b * d + o) * (int64_t)n + t, scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1],
@@ -196,16 +194,16 @@ __global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_produce_vhat(const T*
 // d_ff, contiguous; Q = i, d_model) with one row pointer per Q block plus
 // small constant offsets.  fn(row_offset_elems, dj, ib, jb, g) is called for
 // every quad inside the matrix.
-template <int NQB, class Fn>
+template <class G, class Fn>
 __device__ __forceinline__ void for_state_quads(int j0, int i0, int d, int f, Fn&& fn) {
-  const bool full = j0 + kTile <= f && i0 + 64 * NQB <= d;
-  const int pl = acc_p(0, 0), ql = acc_q<NQB>(0);
+  const bool full = j0 + G::BP <= f && i0 + G::BQ <= d;
+  const int pl = G::acc_p(0, 0), ql = G::acc_q(0);
 #pragma unroll
-  for (int jb = 0; jb < NQB; ++jb) {
+  for (int jb = 0; jb < G::NQB; ++jb) {
     const int i = i0 + ql + jb * 32;
     const int64_t rowoff = (int64_t)i * f + j0 + pl;
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) {
+    for (int ib = 0; ib < G::NPB; ++ib) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int dj = ib * 32 + g * 8;
@@ -216,10 +214,9 @@ __device__ __forceinline__ void for_state_quads(int j0, int i0, int d, int f, Fn
   }
 }
 
-template <int NQB, typename TO>
-__device__ __forceinline__ void store_state(const f32x16 (&acc)[4][NQB], TO* __restrict__ out, int j0, int i0, int d,
-                                            int f) {
-  for_state_quads<NQB>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+template <class G, typename TO, class Acc>
+__device__ __forceinline__ void store_state(const Acc& acc, TO* __restrict__ out, int j0, int i0, int d, int f) {
+  for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
     const f32x16& blk = acc[ib][jb];
     store4(out + ro + dj, blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]);
   });
@@ -228,51 +225,39 @@ __device__ __forceinline__ void store_state(const f32x16 (&acc)[4][NQB], TO* __r
 // Per-chunk delta dW[b, c] = V^_c^T Z_c (Method §3, step 1), fp32 [B, k, d, f].
 // P = d_ff rows of Zt, Q = d_model rows of Vt, K = the chunk's C tokens.
 template <typename T>
-__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_chunk_delta(const T* __restrict__ Zt, const T* __restrict__ Vt,
-                                                           float* __restrict__ dW, int n, int d, int f, int C) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int TP = (f + kTile - 1) / kTile, TQ = (d + kTile - 1) / kTile;
+TTT_GEMM_KERNEL(Wide) void k_chunk_delta(const T* __restrict__ Zt, const T* __restrict__ Vt, float* __restrict__ dW,
+                                         int n, int d, int f, int C_) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (f + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bc = id / per;
   int tp, tq;
   grouped_tile(id - bc * per, TP, TQ, 4, tp, tq);
-  const int k = n / C;
+  const int k = n / C_;
   const int b = bc / k, c = bc - b * k;
-  const int j0 = tp * kTile, i0 = tq * kTile;
+  const int j0 = tp * G::BP, i0 = tq * G::BQ;
   const uint64_t ldb = (uint64_t)n * esz<T>();
-  const unsigned kbytes = (unsigned)C * esz<T>();
+  const unsigned kbytes = (unsigned)C_ * esz<T>();
 
-  DmaOp<false> op, oq;
-  op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C, nullptr, min(kTile, f - j0), ldb, kbytes);
-  oq.init(Vt + ((int64_t)b * d + i0) * n + (int64_t)c * C, nullptr, min(kTile, d - i0), ldb, kbytes);
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  mainloop<T>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
-
-  float* out = dW + (int64_t)bc * d * f;
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    const int i = i0 + acc_q(jb);
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = j0 + acc_p(ib, g);
-        if (i < d && j < f)
-          store4(out + (int64_t)i * f + j, acc[ib][jb][4 * g], acc[ib][jb][4 * g + 1], acc[ib][jb][4 * g + 2],
-                 acc[ib][jb][4 * g + 3]);
-      }
-  }
+  DmaOp<G::NW, G::BP> op;
+  DmaOp<G::NW, G::BQ> oq;
+  op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C_, nullptr, min(G::BP, f - j0), ldb, kbytes);
+  oq.init(Vt + ((int64_t)b * d + i0) * n + (int64_t)c * C_, nullptr, min(G::BQ, d - i0), ldb, kbytes);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
+  store_state<G>(acc, dW + (int64_t)bc * d * f, j0, i0, d, f);
 }
 
 // Exclusive prefix scan over chunks (Method §3, steps 2-3), four elements per
 // thread: Wc[b, c] = W0 + eta * sum_{j<c} dW[b, j]; W_final = W0 + eta * sum_all.
 template <typename T>
-__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_chunk_scan(const float* __restrict__ dW, const T* __restrict__ W0,
-                                                          T* __restrict__ Wc, float* __restrict__ Wf, int k,
-                                                          int64_t df, float eta) {
-  const int64_t e = ((int64_t)blockIdx.x * kThreads + threadIdx.x) * 4;
+__global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW, const T* __restrict__ W0,
+                                                    T* __restrict__ Wc, float* __restrict__ Wf, int k, int64_t df,
+                                                    float eta) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   const int b = blockIdx.y;
   if (e >= df) return;
   const f32x4 w0 = load4(W0 + e);
@@ -288,61 +273,61 @@ __global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_chunk_scan(const floa
          fmaf(eta, s[3], w0[3]));
 }
 
-// Fused delta + scan: each workgroup owns one [256 d_ff x 256 d_model] tile of
+// Fused delta + scan: each workgroup owns one [256 d_ff x 128 d_model] tile of
 // the state and runs its K loop over the whole sequence in token order.  The
 // accumulator starts at W_down0 and the target arrives pre-scaled by eta
 // (Vt = eta V^^T: eta times a delta equals the delta of eta times the target),
 // so after the tokens of chunks 0..c-1 it holds exactly W_c, the state chunk c
 // is applied with.  At each chunk boundary the tile is stored in the operand
-// dtype; after the last chunk in fp32 as W_final.
+// dtype; after the last chunk in fp32 as W_final.  The narrow tile keeps the
+// accumulator at 128 registers per lane, which leaves room for the snapshot
+// stores inside the K loop, and gives 760 tiles at d = 2560, f = 9728.
 template <typename T>
 struct SnapshotHook {
   T* Wc;              // [k, d, f] of this batch row
   int steps_per_chunk, k, j0, i0, d, f;
-  template <int NQB>
-  __device__ __forceinline__ void operator()(int ks, f32x16 (&acc)[4][NQB]) const {
+  template <class A>
+  __device__ __forceinline__ void operator()(int ks, A& acc) const {
     const int done = ks + 1;
     if (done % steps_per_chunk != 0) return;
     const int c = done / steps_per_chunk;
     if (c >= k) return;
-    store_state<NQB>(acc, Wc + (int64_t)c * d * f, j0, i0, d, f);
+    store_state<Narrow>(acc, Wc + (int64_t)c * d * f, j0, i0, d, f);
   }
 };
 
-// Tile: 256 d_ff (P) x 128 d_model (Q).  The smaller accumulator (128 per lane)
-// leaves room in registers for the snapshot stores inside the K loop.
 template <typename T>
-__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_chunk_update_scan(const T* __restrict__ Zt, const T* __restrict__ Vt,
-                                                                 const T* __restrict__ W0, T* __restrict__ Wc,
-                                                                 float* __restrict__ Wf, int n, int d, int f, int C) {
-  constexpr int NQB = 2, BQ = 128;
-  __shared__ __attribute__((aligned(16))) char smem[TileShape<NQB>::kSmem];
-  const int TP = (f + kTile - 1) / kTile, TQ = (d + BQ - 1) / BQ;
+TTT_GEMM_KERNEL(Narrow) void k_chunk_update_scan(const T* __restrict__ Zt, const T* __restrict__ Vt,
+                                                 const T* __restrict__ W0, T* __restrict__ Wc, float* __restrict__ Wf,
+                                                 int n, int d, int f, int C_) {
+  using G = Narrow;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (f + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int b = id / per;
   int tp, tq;
   grouped_tile(id - b * per, TP, TQ, 4, tp, tq);
-  const int k = n / C;
-  const int j0 = tp * kTile, i0 = tq * BQ;
+  const int k = n / C_;
+  const int j0 = tp * G::BP, i0 = tq * G::BQ;
   const uint64_t ldb = (uint64_t)n * esz<T>();
   T* wc = Wc + (int64_t)b * k * d * f;
 
-  DmaOp<false> op;
-  op.init(Zt + ((int64_t)b * f + j0) * n, nullptr, min(kTile, f - j0), ldb, (unsigned)ldb);
-  DmaOp<false, BQ> oq;
-  oq.init(Vt + ((int64_t)b * d + i0) * n, nullptr, min(BQ, d - i0), ldb, (unsigned)ldb);
-  f32x16 acc[4][NQB];
-  zero_acc(acc);
-  for_state_quads<NQB>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+  DmaOp<G::NW, G::BP> op;
+  DmaOp<G::NW, G::BQ> oq;
+  op.init(Zt + ((int64_t)b * f + j0) * n, nullptr, min(G::BP, f - j0), ldb, (unsigned)ldb);
+  oq.init(Vt + ((int64_t)b * d + i0) * n, nullptr, min(G::BQ, d - i0), ldb, (unsigned)ldb);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
     const f32x4 w = load4(W0 + ro + dj);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
   });
-  store_state<NQB>(acc, wc, j0, i0, d, f);                                  // chunk 0: W_down0
-  const SnapshotHook<T> hook{wc, C * esz<T>() / 128, k, j0, i0, d, f};
-  mainloop<T>(op, oq, (int)(ldb / 128), acc, smem, hook);
-  store_state<NQB>(acc, Wf + (int64_t)b * d * f, j0, i0, d, f);            // after the last chunk
+  store_state<G>(acc, wc, j0, i0, d, f);                                  // chunk 0: W_down0
+  const SnapshotHook<T> hook{wc, C_ * esz<T>() / 128, k, j0, i0, d, f};
+  mainloop<T, G>(op, oq, (int)(ldb / 128), acc, smem, hook);
+  store_state<G>(acc, Wf + (int64_t)b * d * f, j0, i0, d, f);            // after the last chunk
 }
 
 // ------------------------------------------------------------------ apply
@@ -350,39 +335,41 @@ __global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_chunk_update_scan(con
 // O_c = Z_c W^T for every chunk (eq. (3)).  P = d_model rows of W, Q = the
 // chunk's tokens, K = d_ff.  W of (b, c) is W + b * wsb + c * wsc.
 template <typename T>
-__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_apply(const T* __restrict__ Z, const T* __restrict__ W, int64_t wsb,
-                                                     int64_t wsc, T* __restrict__ O, int n, int d, int f, int C) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int TP = (d + kTile - 1) / kTile, TQ = (C + kTile - 1) / kTile;
+TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Z, const T* __restrict__ W, int64_t wsb, int64_t wsc,
+                                   T* __restrict__ O, int n, int d, int f, int C_) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bc = id / per;
   int tp, tq;
   grouped_tile(id - bc * per, TP, TQ, 4, tp, tq);
-  const int k = n / C;
+  const int k = n / C_;
   const int b = bc / k, c = bc - b * k;
-  const int i0 = tp * kTile, t0 = tq * kTile;
-  const int64_t row0 = (int64_t)b * n + (int64_t)c * C + t0;
+  const int i0 = tp * G::BP, t0 = tq * G::BQ;
+  const int64_t row0 = (int64_t)b * n + (int64_t)c * C_ + t0;
   const uint64_t ldb = (uint64_t)f * esz<T>();
 
-  DmaOp<false> op, oq;
-  op.init(W + (int64_t)b * wsb + (int64_t)c * wsc + (int64_t)i0 * f, nullptr, min(kTile, d - i0), ldb,
+  DmaOp<G::NW, G::BP> op;
+  DmaOp<G::NW, G::BQ> oq;
+  op.init(W + (int64_t)b * wsb + (int64_t)c * wsc + (int64_t)i0 * f, nullptr, min(G::BP, d - i0), ldb,
           (unsigned)ldb);
-  oq.init(Z + row0 * f, nullptr, min(kTile, C - t0), ldb, (unsigned)ldb);
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  mainloop<T>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
+  oq.init(Z + row0 * f, nullptr, min(G::BQ, C_ - t0), ldb, (unsigned)ldb);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
-  const bool full = i0 + kTile <= d && t0 + kTile <= C;
+  const bool full = i0 + G::BP <= d && t0 + G::BQ <= C_;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = acc_q(j);
+  for (int j = 0; j < G::NQB; ++j) {
+    const int t = G::acc_q(j);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int p = i0 + acc_p(i, g);
-        if (full || (t0 + t < C && p < d))
+        const int p = i0 + G::acc_p(i, g);
+        if (full || (t0 + t < C_ && p < d))
           store4(O + (row0 + t) * d + p, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                  acc[i][j][4 * g + 3]);
       }
@@ -395,44 +382,46 @@ __global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_apply(const T* __rest
 // O_c = Z_c W^T, Rt[b] = (O_c - V^_c)^T [B, d, C].  P = the chunk's tokens,
 // Q = d_model rows of W (W_down0 for c == 0, else this row's state copy).
 template <typename T>
-__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_mse_apply(const T* __restrict__ Z, const T* __restrict__ W, int64_t wsb,
-                                                         T* __restrict__ O, const T* __restrict__ Vt,
-                                                         T* __restrict__ Rt, int n, int d, int f, int C, int c) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int TP = (C + kTile - 1) / kTile, TQ = (d + kTile - 1) / kTile;
+TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Z, const T* __restrict__ W, int64_t wsb,
+                                       T* __restrict__ O, const T* __restrict__ Vt, T* __restrict__ Rt, int n, int d,
+                                       int f, int C_, int c) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (C_ + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int b = id / per;
   int tp, tq;
   grouped_tile(id - b * per, TP, TQ, 4, tp, tq);
-  const int t0 = tp * kTile, i0 = tq * kTile;
-  const int64_t row0 = (int64_t)b * n + (int64_t)c * C;
+  const int t0 = tp * G::BP, i0 = tq * G::BQ;
+  const int64_t row0 = (int64_t)b * n + (int64_t)c * C_;
   const uint64_t ldb = (uint64_t)f * esz<T>();
 
-  DmaOp<false> op, oq;
-  op.init(Z + (row0 + t0) * f, nullptr, min(kTile, C - t0), ldb, (unsigned)ldb);
-  oq.init(W + (int64_t)b * wsb + (int64_t)i0 * f, nullptr, min(kTile, d - i0), ldb, (unsigned)ldb);
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  mainloop<T>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
+  DmaOp<G::NW, G::BP> op;
+  DmaOp<G::NW, G::BQ> oq;
+  op.init(Z + (row0 + t0) * f, nullptr, min(G::BP, C_ - t0), ldb, (unsigned)ldb);
+  oq.init(W + (int64_t)b * wsb + (int64_t)i0 * f, nullptr, min(G::BQ, d - i0), ldb, (unsigned)ldb);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = i0 + acc_q(j);
+  for (int j = 0; j < G::NQB; ++j) {
+    const int i = i0 + G::acc_q(j);
     if (i >= d) continue;
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+    for (int ib = 0; ib < G::NPB; ++ib)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int t = t0 + acc_p(ib, g);
-        if (t >= C) continue;
+        const int t = t0 + G::acc_p(ib, g);
+        if (t >= C_) continue;
         float a[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) a[e] = acc[ib][j][4 * g + e];
 #pragma unroll
         for (int e = 0; e < 4; ++e) O[(row0 + t + e) * d + i] = from_f32<T>(a[e]);
-        const f32x4 v = load4(Vt + ((int64_t)b * d + i) * n + (int64_t)c * C + t);
-        store4(Rt + ((int64_t)b * d + i) * C + t, a[0] - v[0], a[1] - v[1], a[2] - v[2], a[3] - v[3]);
+        const f32x4 v = load4(Vt + ((int64_t)b * d + i) * n + (int64_t)c * C_ + t);
+        store4(Rt + ((int64_t)b * d + i) * C_ + t, a[0] - v[0], a[1] - v[1], a[2] - v[2], a[3] - v[3]);
       }
   }
 }
@@ -442,54 +431,47 @@ __global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_mse_apply(const T* __
 // of Rt, K = C.  The fp32 state lives in Ws [B, d, f] (W_down0 before chunk 0);
 // Wsh (may be null) receives a dtype copy for the next apply.
 template <typename T>
-__global__ __launch_bounds__(kThreads) TTT_ONE_WAVE void k_mse_update(const T* __restrict__ Zt, const T* __restrict__ Rt,
-                                                          const T* __restrict__ W0, float* __restrict__ Ws,
-                                                          T* __restrict__ Wsh, int n, int d, int f, int C, int c,
-                                                          float scale) {
-  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  const int TP = (f + kTile - 1) / kTile, TQ = (d + kTile - 1) / kTile;
+TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __restrict__ Rt, const T* __restrict__ W0,
+                                        float* __restrict__ Ws, T* __restrict__ Wsh, int n, int d, int f, int C_,
+                                        int c, float scale) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (f + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int b = id / per;
   int tp, tq;
   grouped_tile(id - b * per, TP, TQ, 4, tp, tq);
-  const int j0 = tp * kTile, i0 = tq * kTile;
-  const unsigned kbytes = (unsigned)C * esz<T>();
+  const int j0 = tp * G::BP, i0 = tq * G::BQ;
+  const unsigned kbytes = (unsigned)C_ * esz<T>();
 
-  DmaOp<false> op, oq;
-  op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C, nullptr, min(kTile, f - j0), (uint64_t)n * esz<T>(),
+  DmaOp<G::NW, G::BP> op;
+  DmaOp<G::NW, G::BQ> oq;
+  op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C_, nullptr, min(G::BP, f - j0), (uint64_t)n * esz<T>(),
           kbytes);
-  oq.init(Rt + ((int64_t)b * d + i0) * C, nullptr, min(kTile, d - i0), (uint64_t)kbytes, kbytes);
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  mainloop<T>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
+  oq.init(Rt + ((int64_t)b * d + i0) * C_, nullptr, min(G::BQ, d - i0), (uint64_t)kbytes, kbytes);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
 
   float* ws = Ws + (int64_t)b * d * f;
   T* wsh = Wsh ? Wsh + (int64_t)b * d * f : nullptr;
+  for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+    const int64_t o = ro + dj;
+    const f32x4 w = (c == 0) ? load4(W0 + o) : load4(ws + o);
+    float nw[4];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    const int i = i0 + acc_q(jb);
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = j0 + acc_p(ib, g);
-        if (i < d && j < f) {
-          const int64_t o = (int64_t)i * f + j;
-          const f32x4 w = (c == 0) ? load4(W0 + o) : load4(ws + o);
-          float nw[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) nw[e] = fmaf(-scale, acc[ib][jb][4 * g + e], w[e]);
-          store4(ws + o, nw[0], nw[1], nw[2], nw[3]);
-          if (wsh) store4(wsh + o, nw[0], nw[1], nw[2], nw[3]);
-        }
-      }
-  }
+    for (int e = 0; e < 4; ++e) nw[e] = fmaf(-scale, acc[ib][jb][4 * g + e], w[e]);
+    store4(ws + o, nw[0], nw[1], nw[2], nw[3]);
+    if (wsh) store4(wsh + o, nw[0], nw[1], nw[2], nw[3]);
+  });
 }
 
 // ------------------------------------------------------------------ launchers
 
 static inline unsigned tiles_u(int64_t t) { return (unsigned)t; }
+constexpr int kWB = Wide::BP;       // 256 x 256 tiles
+constexpr int kNP = Narrow::BP, kNQ = Narrow::BQ;
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <typename T>
@@ -507,9 +489,9 @@ hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int 
 }
 
 template <typename T>
-hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int C, float scale, hipStream_t s) {
-  if (batch == 0 || R == 0 || C == 0) return hipSuccess;
-  k_transpose<T><<<dim3((unsigned)(cdiv(C, 64) * cdiv(R, 64)), (unsigned)batch), 256, 0, s>>>(src, dst, R, C, scale);
+hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int Cs, float scale, hipStream_t s) {
+  if (batch == 0 || R == 0 || Cs == 0) return hipSuccess;
+  k_transpose<T><<<dim3((unsigned)(cdiv(Cs, 64) * cdiv(R, 64)), (unsigned)batch), 256, 0, s>>>(src, dst, R, Cs, scale);
   return hipGetLastError();
 }
 
@@ -517,7 +499,7 @@ template <typename T>
 hipError_t launch_produce_z(const T* H, const T* Wg, const T* Wu, T* Z, T* Zt, int64_t rows, int n, int d, int f,
                             hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  k_produce_z<T><<<tiles_u(cdiv(rows, kTile) * cdiv(f, 128)), kThreads, 0, s>>>(H, Wg, Wu, Z, Zt, rows, n, d, f);
+  k_produce_z<T><<<tiles_u(cdiv(rows, kWB) * cdiv(f, kWB / 2)), Wide::NT, 0, s>>>(H, Wg, Wu, Z, Zt, rows, n, d, f);
   return hipGetLastError();
 }
 
@@ -525,15 +507,15 @@ template <typename T>
 hipError_t launch_produce_vhat(const T* Y, const T* WtT, T* Vt, int64_t rows, int n, int d, float scale,
                                hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  k_produce_vhat<T><<<tiles_u(cdiv(rows, kTile) * cdiv(d, kTile)), kThreads, 0, s>>>(Y, WtT, Vt, rows, n, d, scale);
+  k_produce_vhat<T><<<tiles_u(cdiv(rows, kWB) * cdiv(d, kWB)), Wide::NT, 0, s>>>(Y, WtT, Vt, rows, n, d, scale);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n, int d, int f, int C, hipStream_t s) {
-  const int64_t tiles = cdiv(f, kTile) * cdiv(d, kTile) * B * (n / C);
+hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n, int d, int f, int Cs, hipStream_t s) {
+  const int64_t tiles = cdiv(f, kWB) * cdiv(d, kWB) * B * (n / Cs);
   if (tiles == 0) return hipSuccess;
-  k_chunk_delta<T><<<tiles_u(tiles), kThreads, 0, s>>>(Zt, Vt, dW, n, d, f, C);
+  k_chunk_delta<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, dW, n, d, f, Cs);
   return hipGetLastError();
 }
 
@@ -541,42 +523,40 @@ template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
                              hipStream_t s) {
   if (B == 0) return hipSuccess;
-  k_chunk_scan<T><<<dim3((unsigned)cdiv(df / 4, kThreads), (unsigned)B), kThreads, 0, s>>>(dW, W0, Wc, Wf, k, df,
-                                                                                         eta);
+  k_chunk_scan<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(dW, W0, Wc, Wf, k, df, eta);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, int B, int n, int d,
-                                    int f, int C, hipStream_t s) {
-  const int64_t tiles = cdiv(f, kTile) * cdiv(d, 128) * B;
+                                    int f, int Cs, hipStream_t s) {
+  const int64_t tiles = cdiv(f, kNP) * cdiv(d, kNQ) * B;
   if (tiles == 0) return hipSuccess;
-  k_chunk_update_scan<T><<<tiles_u(tiles), kThreads, 0, s>>>(Zt, Vt, W0, Wc, Wf, n, d, f, C);
+  k_chunk_update_scan<T><<<tiles_u(tiles), Narrow::NT, 0, s>>>(Zt, Vt, W0, Wc, Wf, n, d, f, Cs);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_apply(const T* Z, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
+hipError_t launch_apply(const T* Z, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int Cs,
                         hipStream_t s) {
-  const int64_t tiles = cdiv(d, kTile) * cdiv(C, kTile) * B * (n / C);
+  const int64_t tiles = cdiv(d, kWB) * cdiv(Cs, kWB) * B * (n / Cs);
   if (tiles == 0) return hipSuccess;
-  k_apply<T><<<tiles_u(tiles), kThreads, 0, s>>>(Z, W, wsb, wsc, O, n, d, f, C);
+  k_apply<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Z, W, wsb, wsc, O, n, d, f, Cs);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_mse_chunk(const T* Z, const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
-                            T* Rt, int B, int n, int d, int f, int C, int c, float eta, hipStream_t s) {
+                            T* Rt, int B, int n, int d, int f, int Cs, int c, float eta, hipStream_t s) {
   const int64_t df = (int64_t)d * f;
   // the state chunk c is applied with: W_down0 (shared) for c == 0, else this row's copy
   const T* W = (c == 0) ? W0 : Wcur;
   const int64_t wsb = (c == 0) ? 0 : df;
-  k_mse_apply<T><<<tiles_u(cdiv(C, kTile) * cdiv(d, kTile) * B), kThreads, 0, s>>>(Z, W, wsb, O, Vt, Rt, n, d, f, C,
-                                                                                   c);
+  k_mse_apply<T><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Z, W, wsb, O, Vt, Rt, n, d, f, Cs, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_mse_update<T><<<tiles_u(cdiv(f, kTile) * cdiv(d, kTile) * B), kThreads, 0, s>>>(Zt, Rt, W0, Ws, Wsh, n, d, f, C,
-                                                                                   c, eta / (float)C);
+  k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, n, d, f, Cs, c,
+                                                                               eta / (float)Cs);
   return hipGetLastError();
 }
 
