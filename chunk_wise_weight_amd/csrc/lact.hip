@@ -1,15 +1,446 @@
-// LaCT SwiGLU fast-weight kernels (review of "Test-Time Training Done Right",
-// LaCT Model Architecture §1, eq. (3)-(4)).
+// LaCT SwiGLU fast-weight kernels for gfx950 (review of "Test-Time Training
+// Done Right", LaCT Model Architecture §1, eq. (3)-(4); ordering of update and
+// apply, same section).
+//
+// f_W(x) = W2 [silu(W1 x) * (W3 x)], per-chunk loss sum_i (1/2)||f_W(k_i) - v_i||^2,
+// one plain GD step per chunk on (W1, W3, W2) together.  Every (batch row,
+// head) pair -- "bh" below -- is an independent fast weight; each launch
+// covers all of them.  For one chunk step, with X the rows [Q part; K part]
+// that share the current weights (update-then-apply: queries of chunk c-1 and
+// keys of chunk c; apply-then-update: queries and keys of chunk c):
+//   fwd1   A = X W1^T, U = X W3^T, Hh = silu(A) * U        (keys: also A^T, U^T, Hh^T)
+//   fwd2   Y = Hh W2^T; queries: O = Y; keys: R = Y - V    (and R^T)
+//   dh     dH = R W2; dU = dH * silu(A); dA = dH * U * silu'(A)   (stored transposed)
+//   grad   G1 = dA^T K, G3 = dU^T K, G2 = R^T Hh            (split over tokens)
+//   update W -= eta * (sum of the splits), fp32 state plus operand copies
+// Layouts: q, k, v, O [BH, n, dh]; W1, W3 [H, m, dh]; W2 [H, dh, m];
+// states W1f, W3f [BH, m, dh], W2f [BH, dh, m] (fp32).
 #include "gemm.hpp"
 #include "launch.hpp"
 
 namespace ttt {
 
-template <typename T>
-size_t lact_workspace_bytes(int, int, int, int, int, int) { return 0; }
+namespace {
+
+template <typename T> constexpr int esz() { return (int)sizeof(T); }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+constexpr int kSplit = 4;              // token splits of the weight-gradient GEMMs
+
+// Workspace layout (byte offsets), one region per buffer.
+struct LactWs {
+  size_t Kt, Hh, HhT, At, Ut, R, Rt, dAt, dUt, W1s, W3s, W2s, W2Ts, part, total;
+};
+
+inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
 template <typename T>
-hipError_t launch_lact(const LactArgs&, hipStream_t) { return hipErrorNotSupported; }
+LactWs lact_layout(int B, int H, int n, int dh, int m, int C) {
+  const size_t e = sizeof(T), BH = (size_t)B * H, md = (size_t)m * dh;
+  LactWs w{};
+  size_t o = 0;
+  w.Kt = o;   o += al(BH * n * dh * e);           // keys, token-contiguous [BH, dh, n]
+  w.Hh = o;   o += al(2 * BH * C * m * e);        // hidden of [Q part; K part] [2, BH, C, m]
+  w.HhT = o;  o += al(BH * m * C * e);            // key hidden, transposed [BH, m, C]
+  w.At = o;   o += al(BH * m * C * e);            // key pre-activations [BH, m, C]
+  w.Ut = o;   o += al(BH * m * C * e);
+  w.R = o;    o += al(BH * C * dh * e);           // residual f(k) - v [BH, C, dh]
+  w.Rt = o;   o += al(BH * dh * C * e);           // and transposed [BH, dh, C]
+  w.dAt = o;  o += al(BH * m * C * e);
+  w.dUt = o;  o += al(BH * m * C * e);
+  w.W1s = o;  o += al(BH * md * e);               // operand copies of the current state
+  w.W3s = o;  o += al(BH * md * e);
+  w.W2s = o;  o += al(BH * md * e);
+  w.W2Ts = o; o += al(BH * md * e);               // W2^T [BH, m, dh]
+  w.part = o; o += al((size_t)kSplit * BH * 3 * md * 4);   // split-token gradient partials
+  w.total = o;
+  return w;
+}
+
+}  // namespace
+
+// Rows of a chunk step: part 0 = queries of chunk qc (nq rows), part 1 = keys of
+// chunk kc (nk rows).  Row tiles never straddle the parts.
+struct StepRows {
+  int nq, nk, qc, kc;
+};
+
+__host__ __device__ constexpr int cdiv_d(int a, int b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ fwd1
+
+// A = X W1^T, U = X W3^T over the rows X of both parts.  P = rows (tokens),
+// Q = W1 / W3 rows in alternating 32-row blocks.  Writes Hh [2, BH, C, m] for
+// both parts, and for the key part A^T, U^T, Hh^T [BH, m, C].
+template <typename T>
+TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ W1s,
+                                       const T* __restrict__ W3s, T* __restrict__ Hh, T* __restrict__ HhT,
+                                       T* __restrict__ At, T* __restrict__ Ut, int BH, int n, int dh, int m, int C,
+                                       StepRows sr) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int tq_n = (m + G::BQ / 2 - 1) / (G::BQ / 2);
+  const int tpq = (sr.nq + G::BP - 1) / G::BP, tpk = (sr.nk + G::BP - 1) / G::BP;
+  const int TP = tpq + tpk, per = TP * tq_n;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = id / per;
+  int tp, tq;
+  grouped_tile(id - bh * per, TP, tq_n, 4, tp, tq);
+  const int part = tp < tpq ? 0 : 1;
+  const int r0 = (part ? tp - tpq : tp) * G::BP;
+  const int nrows = part ? sr.nk : sr.nq;
+  const T* X = (part ? k : q) + ((int64_t)bh * n + (int64_t)(part ? sr.kc : sr.qc) * C) * dh;
+  const int j0 = tq * (G::BQ / 2);
+  const uint64_t ldb = (uint64_t)dh * esz<T>();
+  const int64_t md = (int64_t)m * dh;
+
+  DmaOp<G::NW, G::BP> op;
+  op.init(X + (int64_t)r0 * dh, nullptr, min(G::BP, nrows - r0), ldb, (unsigned)ldb);
+  DmaOp<G::NW, G::BQ, true> oq;
+  oq.init(W1s + bh * md + (int64_t)j0 * dh, W3s + bh * md + (int64_t)j0 * dh, min(G::BQ / 2, m - j0), ldb,
+          (unsigned)ldb);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
+
+  const int j = j0 + (wave_id() % G::WQ) * 32 + (lane_id() & 31);
+  if (j >= m) return;
+  T* hh = Hh + ((int64_t)part * BH + bh) * C * m;
+  const int64_t tb = ((int64_t)bh * m + j) * C;     // row j of the [BH, m, C] buffers
+#pragma unroll
+  for (int i = 0; i < G::NPB; ++i) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r = r0 + G::acc_p(i, g);
+      if (r >= nrows) continue;
+      float a[4], u[4], h[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = acc[i][0][4 * g + e];
+        u[e] = acc[i][1][4 * g + e];
+        h[e] = silu_f(a[e]) * u[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hh[(int64_t)(r + e) * m + j] = from_f32<T>(h[e]);
+      if (part) {
+        store4(HhT + tb + r, h[0], h[1], h[2], h[3]);
+        store4(At + tb + r, a[0], a[1], a[2], a[3]);
+        store4(Ut + tb + r, u[0], u[1], u[2], u[3]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ fwd2
+
+// Y = Hh W2^T.  P = dh rows of W2s [BH, dh, m], Q = rows of Hh (both parts).
+// Query rows: O[bh, qc C + r, :] = Y.  Key rows: R = Y - V (R [BH, C, dh]) and
+// R^T [BH, dh, C].
+template <typename T>
+TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __restrict__ W2s, const T* __restrict__ v,
+                                       T* __restrict__ O, T* __restrict__ R, T* __restrict__ Rt, int BH, int n, int dh,
+                                       int m, int C, StepRows sr) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (dh + G::BP - 1) / G::BP;
+  const int tqq = (sr.nq + G::BQ - 1) / G::BQ, tqk = (sr.nk + G::BQ - 1) / G::BQ;
+  const int TQ = tqq + tqk, per = TP * TQ;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = id / per;
+  int tp, tq;
+  grouped_tile(id - bh * per, TP, TQ, 4, tp, tq);
+  const int part = tq < tqq ? 0 : 1;
+  const int r0 = (part ? tq - tqq : tq) * G::BQ;
+  const int nrows = part ? sr.nk : sr.nq;
+  const int i0 = tp * G::BP;
+  const uint64_t ldb = (uint64_t)m * esz<T>();
+
+  DmaOp<G::NW, G::BP> op;
+  DmaOp<G::NW, G::BQ> oq;
+  op.init(W2s + (int64_t)bh * dh * m + (int64_t)i0 * m, nullptr, min(G::BP, dh - i0), ldb, (unsigned)ldb);
+  oq.init(Hh + (((int64_t)part * BH + bh) * C + r0) * m, nullptr, min(G::BQ, nrows - r0), ldb, (unsigned)ldb);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
+
+#pragma unroll
+  for (int jq = 0; jq < G::NQB; ++jq) {
+    const int r = r0 + G::acc_q(jq);
+    if (r >= nrows) continue;
+#pragma unroll
+    for (int ib = 0; ib < G::NPB; ++ib)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int i = i0 + G::acc_p(ib, g);
+        if (i >= dh) continue;
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = acc[ib][jq][4 * g + e];
+        if (!part) {
+          store4(O + ((int64_t)bh * n + (int64_t)sr.qc * C + r) * dh + i, y[0], y[1], y[2], y[3]);
+        } else {
+          const f32x4 vv = load4(v + ((int64_t)bh * n + (int64_t)sr.kc * C + r) * dh + i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] -= vv[e];
+          store4(R + ((int64_t)bh * C + r) * dh + i, y[0], y[1], y[2], y[3]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Rt[((int64_t)bh * dh + i + e) * C + r] = from_f32<T>(y[e]);
+        }
+      }
+  }
+}
+
+// ------------------------------------------------------------------ dh
+
+// dH = R W2 [C, m]; P = tokens (R rows), Q = m rows of W2^T.  Epilogue: the
+// SiLU-gate backward, written token-contiguous: dU^T = (dH * silu(A))^T,
+// dA^T = (dH * U * silu'(A))^T, silu'(a) = s (1 + a (1 - s)), s = sigmoid(a).
+template <typename T>
+TTT_GEMM_KERNEL(Wide) void k_lact_dh(const T* __restrict__ R, const T* __restrict__ W2Ts, const T* __restrict__ At,
+                                     const T* __restrict__ Ut, T* __restrict__ dAt, T* __restrict__ dUt, int BH, int dh,
+                                     int m, int C, int nk) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (nk + G::BP - 1) / G::BP, TQ = (m + G::BQ - 1) / G::BQ, per = TP * TQ;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = id / per;
+  int tp, tq;
+  grouped_tile(id - bh * per, TP, TQ, 4, tp, tq);
+  const int t0 = tp * G::BP, j0 = tq * G::BQ;
+  const uint64_t ldb = (uint64_t)dh * esz<T>();
+
+  DmaOp<G::NW, G::BP> op;
+  DmaOp<G::NW, G::BQ> oq;
+  op.init(R + ((int64_t)bh * C + t0) * dh, nullptr, min(G::BP, nk - t0), ldb, (unsigned)ldb);
+  oq.init(W2Ts + (int64_t)bh * m * dh + (int64_t)j0 * dh, nullptr, min(G::BQ, m - j0), ldb, (unsigned)ldb);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
+
+#pragma unroll
+  for (int jq = 0; jq < G::NQB; ++jq) {
+    const int j = j0 + G::acc_q(jq);
+    if (j >= m) continue;
+    const int64_t rowj = ((int64_t)bh * m + j) * C;
+#pragma unroll
+    for (int ib = 0; ib < G::NPB; ++ib)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int t = t0 + G::acc_p(ib, g);
+        if (t >= nk) continue;
+        const f32x4 a = load4(At + rowj + t), u = load4(Ut + rowj + t);
+        float du[4], da[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float dh_ = acc[ib][jq][4 * g + e];
+          const float s = 1.0f / (1.0f + __expf(-a[e]));
+          du[e] = dh_ * a[e] * s;
+          da[e] = dh_ * u[e] * s * (1.0f + a[e] * (1.0f - s));
+        }
+        store4(dUt + rowj + t, du[0], du[1], du[2], du[3]);
+        store4(dAt + rowj + t, da[0], da[1], da[2], da[3]);
+      }
+  }
+}
+
+// ------------------------------------------------------------------ weight gradients
+
+// Three contractions over the chunk's tokens, split kSplit ways along the
+// tokens, written as fp32 partials part[s][bh][w] (w = 0: G1 [m, dh], 1: G3
+// [m, dh], 2: G2 [dh, m]):
+//   G1[j][i] = sum_t dA[t][j] K[t][i]   P = i (K^T rows), Q = j (dA^T rows)
+//   G3[j][i] = sum_t dU[t][j] K[t][i]   P = i (K^T rows), Q = j (dU^T rows)
+//   G2[i][j] = sum_t R[t][i] Hh[t][j]   P = j (Hh^T rows), Q = i (R^T rows)
+template <typename T>
+TTT_GEMM_KERNEL(Wide) void k_lact_grad(const T* __restrict__ Kt, const T* __restrict__ dAt, const T* __restrict__ dUt,
+                                       const T* __restrict__ HhT, const T* __restrict__ Rt, float* __restrict__ part,
+                                       int BH, int n, int dh, int m, int C, int kc, int nk, int kslice) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int tA = cdiv_d(dh, G::BP) * cdiv_d(m, G::BQ);   // tiles of G1 and of G3
+  const int tB = cdiv_d(m, G::BP) * cdiv_d(dh, G::BQ);   // tiles of G2
+  const int per = 2 * tA + tB;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int sb = id / per;
+  int r = id - sb * per;
+  const int s = sb % kSplit, bh = sb / kSplit;
+  const int which = r < tA ? 0 : (r < 2 * tA ? 1 : 2);
+  r -= which == 0 ? 0 : (which == 1 ? tA : 2 * tA);
+  const int PD = which < 2 ? dh : m, QD = which < 2 ? m : dh;     // P and Q extents
+  int tp, tq;
+  grouped_tile(r, cdiv_d(PD, G::BP), cdiv_d(QD, G::BQ), 4, tp, tq);
+  const int p0 = tp * G::BP, q0 = tq * G::BQ;
+  const int tk0 = s * kslice;
+  const int kl = max(0, min(kslice, nk - tk0));
+  const unsigned kbytes = (unsigned)kl * esz<T>();
+  const T* Pbase;
+  const T* Qbase;
+  uint64_t pld, qld;
+  if (which < 2) {
+    Pbase = Kt + ((int64_t)bh * dh + p0) * n + (int64_t)kc * C + tk0;
+    pld = (uint64_t)n * esz<T>();
+    Qbase = (which == 0 ? dAt : dUt) + ((int64_t)bh * m + q0) * C + tk0;
+    qld = (uint64_t)C * esz<T>();
+  } else {
+    Pbase = HhT + ((int64_t)bh * m + p0) * C + tk0;
+    pld = (uint64_t)C * esz<T>();
+    Qbase = Rt + ((int64_t)bh * dh + q0) * C + tk0;
+    qld = (uint64_t)C * esz<T>();
+  }
+  DmaOp<G::NW, G::BP> op;
+  DmaOp<G::NW, G::BQ> oq;
+  op.init(Pbase, nullptr, min(G::BP, PD - p0), pld, kbytes);
+  oq.init(Qbase, nullptr, min(G::BQ, QD - q0), qld, kbytes);
+  f32x16 acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
+
+  const int64_t md = (int64_t)m * dh;
+  float* out = part + (((int64_t)s * BH + bh) * 3 + which) * md;
+#pragma unroll
+  for (int jq = 0; jq < G::NQB; ++jq) {
+    const int qi = q0 + G::acc_q(jq);
+    if (qi >= QD) continue;
+#pragma unroll
+    for (int ib = 0; ib < G::NPB; ++ib)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int pi = p0 + G::acc_p(ib, g);
+        if (pi < PD)
+          store4(out + (int64_t)qi * PD + pi, acc[ib][jq][4 * g], acc[ib][jq][4 * g + 1], acc[ib][jq][4 * g + 2],
+                 acc[ib][jq][4 * g + 3]);
+      }
+  }
+}
+
+// ------------------------------------------------------------------ state update
+
+// W -= eta * sum_s part[s]; writes the fp32 state and the operand copies
+// (W2 also transposed).  Four elements per thread; grid.y = bh * 3 + w.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lact_update(const float* __restrict__ part, float* __restrict__ W1f,
+                                                     float* __restrict__ W3f, float* __restrict__ W2f,
+                                                     T* __restrict__ W1s, T* __restrict__ W3s, T* __restrict__ W2s,
+                                                     T* __restrict__ W2Ts, int BH, int dh, int m, float eta) {
+  const int64_t md = (int64_t)m * dh;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= md) return;
+  const int bh = blockIdx.y / 3, w = blockIdx.y % 3;
+  f32x4 gsum = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kSplit; ++s) gsum += load4(part + (((int64_t)s * BH + bh) * 3 + w) * md + e);
+  float* Wf = (w == 0 ? W1f : (w == 1 ? W3f : W2f)) + (int64_t)bh * md + e;
+  T* Ws = (w == 0 ? W1s : (w == 1 ? W3s : W2s)) + (int64_t)bh * md + e;
+  f32x4 x = load4(Wf);
+  x -= eta * gsum;
+  store4(Wf, x[0], x[1], x[2], x[3]);
+  store4(Ws, x[0], x[1], x[2], x[3]);
+  if (w == 2) {   // W2 [dh, m] element e = (i, j) -> W2^T [m, dh] element (j, i)
+    const int i = (int)(e / m), j = (int)(e % m);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) W2Ts[(int64_t)bh * md + (int64_t)(j + q) * dh + i] = from_f32<T>(x[q]);
+  }
+}
+
+// Initial state of every (batch row, head) from the heads' initial weights.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lact_init(const T* __restrict__ W1, const T* __restrict__ W3,
+                                                   const T* __restrict__ W2, float* __restrict__ W1f,
+                                                   float* __restrict__ W3f, float* __restrict__ W2f,
+                                                   T* __restrict__ W1s, T* __restrict__ W3s, T* __restrict__ W2s,
+                                                   T* __restrict__ W2Ts, int H, int dh, int m) {
+  const int64_t md = (int64_t)m * dh;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= md) return;
+  const int bh = blockIdx.y / 3, w = blockIdx.y % 3, h = bh % H;
+  const T* src = (w == 0 ? W1 : (w == 1 ? W3 : W2)) + (int64_t)h * md + e;
+  const f32x4 x = load4(src);
+  float* Wf = (w == 0 ? W1f : (w == 1 ? W3f : W2f)) + (int64_t)bh * md + e;
+  T* Ws = (w == 0 ? W1s : (w == 1 ? W3s : W2s)) + (int64_t)bh * md + e;
+  store4(Wf, x[0], x[1], x[2], x[3]);
+  store4(Ws, x[0], x[1], x[2], x[3]);
+  if (w == 2) {
+    const int i = (int)(e / m), j = (int)(e % m);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) W2Ts[(int64_t)bh * md + (int64_t)(j + q) * dh + i] = from_f32<T>(x[q]);
+  }
+}
+
+// ------------------------------------------------------------------ host driver
+
+template <typename T>
+size_t lact_workspace_bytes(int B, int H, int n, int dh, int m, int C) {
+  return lact_layout<T>(B, H, n, dh, m, C).total;
+}
+
+template <typename T>
+hipError_t launch_lact(const LactArgs& a, hipStream_t s) {
+  const int BH = a.B * a.H, n = a.n, dh = a.dh, m = a.m, C = a.C;
+  const int k = n / C;
+  const LactWs L = lact_layout<T>(a.B, a.H, n, dh, m, C);
+  T* Kt = (T*)(a.ws + L.Kt);
+  T* Hh = (T*)(a.ws + L.Hh);
+  T* HhT = (T*)(a.ws + L.HhT);
+  T* At = (T*)(a.ws + L.At);
+  T* Ut = (T*)(a.ws + L.Ut);
+  T* R = (T*)(a.ws + L.R);
+  T* Rt = (T*)(a.ws + L.Rt);
+  T* dAt = (T*)(a.ws + L.dAt);
+  T* dUt = (T*)(a.ws + L.dUt);
+  T* W1s = (T*)(a.ws + L.W1s);
+  T* W3s = (T*)(a.ws + L.W3s);
+  T* W2s = (T*)(a.ws + L.W2s);
+  T* W2Ts = (T*)(a.ws + L.W2Ts);
+  float* part = (float*)(a.ws + L.part);
+  const T* q = (const T*)a.q;
+  const T* kk = (const T*)a.k;
+  const T* v = (const T*)a.v;
+  T* O = (T*)a.O;
+  const int64_t md = (int64_t)m * dh;
+  const dim3 ew((unsigned)cdiv(md / 4, 256), (unsigned)(BH * 3));
+  hipError_t e;
+
+  k_lact_init<T><<<ew, 256, 0, s>>>((const T*)a.W1, (const T*)a.W3, (const T*)a.W2, a.W1f, a.W3f, a.W2f, W1s, W3s,
+                                    W2s, W2Ts, a.H, dh, m);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (n == 0) return hipSuccess;
+  if ((e = launch_transpose<T>(kk, Kt, BH, n, dh, 1.0f, s)) != hipSuccess) return e;
+
+  const int kslice = (int)(cdiv(cdiv(C, kSplit), 64) * 64);
+  const bool upd_first = a.order == 0;
+  const int steps = upd_first ? k + 1 : k;
+  for (int c = 0; c < steps; ++c) {
+    StepRows sr;
+    if (upd_first) {
+      sr.qc = c - 1;
+      sr.kc = c;
+      sr.nq = c >= 1 ? C : 0;
+      sr.nk = c < k ? C : 0;
+    } else {
+      sr.qc = sr.kc = c;
+      sr.nq = sr.nk = C;
+    }
+    const int tp1 = (int)(cdiv(sr.nq, Wide::BP) + cdiv(sr.nk, Wide::BP));
+    k_lact_fwd1<T><<<(unsigned)(tp1 * cdiv(m, Wide::BQ / 2) * BH), Wide::NT, 0, s>>>(q, kk, W1s, W3s, Hh, HhT, At, Ut,
+                                                                                   BH, n, dh, m, C, sr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int tq2 = (int)(cdiv(sr.nq, Wide::BQ) + cdiv(sr.nk, Wide::BQ));
+    k_lact_fwd2<T><<<(unsigned)(cdiv(dh, Wide::BP) * tq2 * BH), Wide::NT, 0, s>>>(Hh, W2s, v, O, R, Rt, BH, n, dh, m,
+                                                                                C, sr);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (sr.nk == 0) continue;
+    k_lact_dh<T><<<(unsigned)(cdiv(sr.nk, Wide::BP) * cdiv(m, Wide::BQ) * BH), Wide::NT, 0, s>>>(
+        R, W2Ts, At, Ut, dAt, dUt, BH, dh, m, C, sr.nk);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t tg = (2 * cdiv(dh, Wide::BP) * cdiv(m, Wide::BQ) + cdiv(m, Wide::BP) * cdiv(dh, Wide::BQ)) *
+                       (int64_t)kSplit * BH;
+    k_lact_grad<T><<<(unsigned)tg, Wide::NT, 0, s>>>(Kt, dAt, dUt, HhT, Rt, part, BH, n, dh, m, C, sr.kc, sr.nk,
+                                                     kslice);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_lact_update<T><<<ew, 256, 0, s>>>(part, a.W1f, a.W3f, a.W2f, W1s, W3s, W2s, W2Ts, BH, dh, m, a.eta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
 
 template size_t lact_workspace_bytes<float>(int, int, int, int, int, int);
 template size_t lact_workspace_bytes<bf16>(int, int, int, int, int, int);

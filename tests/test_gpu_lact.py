@@ -1,0 +1,119 @@
+"""GPU parity of the LaCT SwiGLU fast-weight layer against the float64 oracle.
+
+Calls go through the C ABI (ttt_lact_swiglu).  Tolerances as for the
+In-Place layer: relative Frobenius <= 1e-4 (fp32), <= 2e-2 (bf16 storage,
+fp32 accumulation and fp32 states); the update W_final - W0 is compared on its
+own as well so that the learned part is pinned, not just the initial weights.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunk_wise_weight_amd as cw
+import ttt_inputs as ti
+from oracle import lact as olact
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def cfg_small(dtype="f32", order="update_then_apply", B=1, H=2, n=512, dh=64, m=128, C=128, eta=1.0, seed=5):
+    return ti.LactConfig("small", B, H, n, dh, m, C, eta, order, dtype, seed=seed)
+
+
+def run(cfg):
+    x = ti.lact_inputs(cfg)
+    g = {k: v.cuda() for k, v in x.items()}
+    O, W1f, W3f, W2f = cw.ttt_lact_swiglu(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta,
+                                          cfg.order)
+    torch.cuda.synchronize()
+    return x, O, W1f, W3f, W2f
+
+
+def check(cfg, x, O, W1f, W3f, W2f, tol=None):
+    tol = tol or TOL[cfg.dtype]
+    ref = olact.lact_layer(*(ti.to_f64(x[k]) for k in ("q", "k", "v", "W1", "W3", "W2")), cfg.chunk, cfg.eta,
+                           cfg.order)
+    Oref, W1r, W3r, W2r = ref
+    errs = {"O": rel(f64(O), Oref)}
+    for name, got, want, init in (("W1", W1f, W1r, x["W1"]), ("W3", W3f, W3r, x["W3"]), ("W2", W2f, W2r, x["W2"])):
+        w0 = ti.to_f64(init)[None]
+        errs[name] = rel(f64(got), want)
+        errs[name + "_delta"] = rel(f64(got) - w0, want - w0)
+    assert all(v < tol for v in errs.values()), errs
+    return errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
+def test_lact_small(dtype, order):
+    cfg = cfg_small(dtype, order)
+    check(cfg, *run(cfg))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lact_ragged_dims_and_batch(dtype):
+    # head_dim and hidden not multiples of the 64-element K step or the tiles; 2 x 2 (batch, head) states
+    cfg = cfg_small(dtype, B=2, H=2, n=384, dh=72, m=136, C=96, eta=0.7, seed=9)
+    check(cfg, *run(cfg))
+
+
+def test_lact_eta_zero_is_plain_swiglu():
+    cfg = cfg_small("bf16", eta=0.0)
+    x, O, W1f, W3f, W2f = run(cfg)
+    for h in range(cfg.heads):
+        ref = olact.swiglu_apply(ti.to_f64(x["q"])[0, h], ti.to_f64(x["W1"])[h], ti.to_f64(x["W3"])[h],
+                                 ti.to_f64(x["W2"])[h])
+        assert rel(f64(O[0, h]), ref) < TOL["bf16"]
+    assert np.array_equal(f64(W1f[0]), ti.to_f64(x["W1"]))
+    assert np.array_equal(f64(W2f[0]), ti.to_f64(x["W2"]))
+
+
+def test_lact_single_chunk_full_batch_step():
+    cfg = cfg_small("f32", n=256, C=256)
+    check(cfg, *run(cfg))
+
+
+def test_lact_causality_update_then_apply():
+    cfg = cfg_small("bf16", n=512, C=128)
+    x = ti.lact_inputs(cfg)
+    g = {k: v.cuda() for k, v in x.items()}
+    args = lambda gg: (gg["q"], gg["k"], gg["v"], gg["W1"], gg["W3"], gg["W2"], cfg.chunk, cfg.eta, cfg.order)
+    O = cw.ttt_lact_swiglu(*args(g))[0]
+    g2 = dict(g)
+    for name in ("q", "k", "v"):
+        g2[name] = g[name].clone()
+        g2[name][:, :, 2 * cfg.chunk:] = g[name][:, :, 2 * cfg.chunk:].flip(2)
+    O2 = cw.ttt_lact_swiglu(*args(g2))[0]
+    torch.cuda.synchronize()
+    assert torch.equal(O[:, :, : 2 * cfg.chunk], O2[:, :, : 2 * cfg.chunk])
+    assert not torch.equal(O[:, :, 2 * cfg.chunk:], O2[:, :, 2 * cfg.chunk:])
+
+
+def test_lact_workload_shapes_two_chunks():
+    """The workload's head_dim 512, hidden 1024, chunk 4096, eta 1, on two chunks of one head."""
+    cfg = ti.workload("lact_bf16_256k").with_(heads=1, seq_len=8192)
+    check(cfg, *run(cfg))
+
+
+@pytest.mark.slow
+def test_lact_full_size_first_chunks_sampled():
+    cfg = ti.workload("lact_bf16_256k")
+    x, O, W1f, W3f, W2f = run(cfg)
+    assert torch.isfinite(O).all() and torch.isfinite(W1f).all() and torch.isfinite(W2f).all()
+    C = cfg.chunk
+    sub = {k: ti.to_f64(v[:, :1, : 2 * C]) if k in ("q", "k", "v") else ti.to_f64(v[:1])
+           for k, v in x.items()}
+    Oref, *_ = olact.lact_layer(sub["q"], sub["k"], sub["v"], sub["W1"], sub["W3"], sub["W2"], C, cfg.eta, cfg.order)
+    assert rel(f64(O[:, :1, : 2 * C]), Oref) < TOL["bf16"]
