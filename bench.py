@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the 32K-context secondary figure")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (reference point for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -62,6 +64,28 @@ def kernel_bytes(cfg, esz=2):
         "update_scan": esz * (T * f + T * d + d * f + B * k * d * f) + 4 * B * d * f,
         "apply": esz * (T * f + B * k * d * f + T * d),
     }
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when there is none for this workload or the kernel sources changed since."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    h = hashlib.sha256()
+    for f in ("common.hpp", "gemm.hpp", "inplace.hip"):
+        with open(os.path.join(ROOT, "chunk_wise_weight_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if rec.get("source_sha256") != h.hexdigest():
+        return None
+    return rec["bytes_per_launch"].get("k_" + kernel)
 
 
 def bench_inplace_dot(cfg, steps, warmup):
@@ -185,12 +209,29 @@ def cpu_baseline(cfg, target_s):
             "seconds": t1}
 
 
+def calibrate_copy(mib, steps):
+    """A plain copy of known size: reads and writes mib MiB once per launch."""
+    import torch
+
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": steps}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import torch
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy, args.steps)
+        return
 
     import ttt_inputs as ti
 
@@ -221,7 +262,8 @@ def main():
         dom = max(per, key=per.get)
         ach = fl[dom] / (per[dom] * 1e-3) / 1e12
         out["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK[dtype],
-                           "unit": "TFLOP/s", "frac": round(ach / PEAK[dtype], 4), "traffic": None}
+                           "unit": "TFLOP/s", "frac": round(ach / PEAK[dtype], 4),
+                           "traffic": measured_traffic(cfg.name, dom)}
     else:
         wall, per = bench_generic(cfg, args.steps, args.warmup)
         ms = per["layer"]
