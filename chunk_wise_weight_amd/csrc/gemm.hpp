@@ -3,12 +3,12 @@
 // A workgroup of NW = WP x WQ waves owns a BP x BQ tile acc[p][q] =
 // sum_k P[p][k] * Q[q][k] and walks K in steps of 128 bytes (64 bf16 or 32
 // fp32).  Both operands are K-contiguous in global memory.  Wave (wp, wq)
-// owns NPB x NQB 32x32 MFMA accumulator blocks (BP = 32 NPB WP,
-// BQ = 32 NQB WQ).  Two shapes are used:
-//   Wide   = 8 waves, 2 x 4, 4 x 2 blocks: 256 x 256 tile, 128 accumulators
+// owns NPB x NQB 16x16 MFMA accumulator blocks (BP = 16 NPB WP,
+// BQ = 16 NQB WQ).  Two shapes are used:
+//   Wide   = 8 waves, 2 x 4, 8 x 4 blocks: 256 x 256 tile, 128 accumulators
 //            per lane, two waves per SIMD so that one wave's LDS and barrier
 //            waits are covered by the other's MFMAs;
-//   Narrow = 4 waves, 2 x 2, 4 x 2 blocks: 256 x 128 tile, for grids where a
+//   Narrow = 4 waves, 2 x 2, 8 x 4 blocks: 256 x 128 tile, for grids where a
 //            256 x 256 tiling would leave most of a wave of workgroups idle.
 //
 // Global -> LDS: buffer_load_dwordx4 ... lds (LDS DMA).  One instruction moves
@@ -23,11 +23,14 @@
 // (BP + BQ) x 128 B: step k+1 is in flight while step k is multiplied; one
 // barrier per step.
 //
-// MFMA mapping (v_mfma_f32_32x32x16_bf16, or 4 x v_mfma_f32_32x32x2_f32 for
-// fp32): P feeds the instruction's A slot, Q its B slot.  A lane therefore
-// holds one q index and, per group of 4 registers, 4 consecutive p indices, so
-// epilogues store 4 consecutive p values at once: whichever output dimension
-// is contiguous in memory is mapped to P.
+// MFMA mapping (v_mfma_f32_16x16x32_bf16, or 4 x v_mfma_f32_16x16x4_f32 for
+// fp32): P feeds the instruction's A slot, Q its B slot.  Operand lane l holds
+// row l & 15 of its block and the 16 bytes of chunk 4 g + (l >> 4) of the K
+// step (group g = 0, 1).  The 16x16 shape is preferred to 32x32x16: it moves a
+// quarter of the accumulator per instruction and sustains a higher MFMA rate
+// on random data.  Result lane l holds 4 consecutive p indices at one q index,
+// so epilogues store 4 consecutive p values at once: whichever output
+// dimension is contiguous in memory is mapped to P.
 #pragma once
 #include "common.hpp"
 
@@ -45,19 +48,22 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 template <int WP_, int WQ_, int NPB_, int NQB_>
 struct TileCfg {
   static constexpr int WP = WP_, WQ = WQ_, NPB = NPB_, NQB = NQB_;
+  static constexpr int BM = 16;                 // MFMA block edge
+  static constexpr int GPB = 1;                 // groups of 4 accumulators per block and lane
+  using Frag = f32x4;                           // one block's accumulators in one lane
   static constexpr int NW = WP * WQ, NT = 64 * NW;
-  static constexpr int BP = 32 * NPB * WP, BQ = 32 * NQB * WQ;
+  static constexpr int BP = BM * NPB * WP, BQ = BM * NQB * WQ;
   static constexpr int PBytes = BP * 128, QBytes = BQ * 128;
   static constexpr int Stage = PBytes + QBytes, Smem = 2 * Stage;
   // tile coordinates of this lane's accumulators: block (i, j), register
   // group g covers p = acc_p(i, g) + 0..3 at q = acc_q(j)
   __device__ static __forceinline__ int acc_p(int i, int g) {
-    return (wave_id() / WQ) * (32 * NPB) + i * 32 + g * 8 + (lane_id() >> 5) * 4;
+    return (wave_id() / WQ) * (BM * NPB) + i * BM + g * 8 + (lane_id() >> 4) * 4;
   }
-  __device__ static __forceinline__ int acc_q(int j) { return (wave_id() % WQ) * (32 * NQB) + j * 32 + (lane_id() & 31); }
+  __device__ static __forceinline__ int acc_q(int j) { return (wave_id() % WQ) * (BM * NQB) + j * BM + (lane_id() & 15); }
 };
-using Wide = TileCfg<2, 4, 4, 2>;
-using Narrow = TileCfg<2, 2, 4, 2>;
+using Wide = TileCfg<2, 4, 8, 4>;
+using Narrow = TileCfg<2, 2, 8, 4>;
 
 // Kernel attributes: NT threads, and the number of waves per SIMD the register
 // budget is planned for (the scheduler then spends registers on keeping LDS
@@ -141,42 +147,42 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 
 // ---------------------------------------------------------------- MFMA step
 
-__device__ __forceinline__ void mma(f32x16& acc, u32x4 p, u32x4 q, bf16*) {
-  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, p), __builtin_bit_cast(bf16x8, q),
+__device__ __forceinline__ void mma(f32x4& acc, u32x4 p, u32x4 q, bf16*) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, p), __builtin_bit_cast(bf16x8, q),
                                                 acc, 0, 0, 0);
 }
-__device__ __forceinline__ void mma(f32x16& acc, u32x4 p, u32x4 q, float*) {
-  // Lane-half h holds k = 4h + e of this 8-wide group in element e: four
-  // 32x32x2 steps, step e contracting {e, 4 + e}, cover all eight.
+__device__ __forceinline__ void mma(f32x4& acc, u32x4 p, u32x4 q, float*) {
+  // Lane quarter h holds k = 4h + e of this 16-wide group in element e: four
+  // 16x16x4 steps, step e contracting {e, 4 + e, 8 + e, 12 + e}, cover all 16.
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(p[e]), __uint_as_float(q[e]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(p[e]), __uint_as_float(q[e]), acc, 0, 0, 0);
 }
 
 template <class C, class PF, class QF>
 __device__ __forceinline__ void load_frags(const char* tp, const char* tq, int g, PF& pf, QF& qf) {
   const int lane = lane_id(), w = wave_id();
-  const int prow = (w / C::WQ) * (32 * C::NPB) + (lane & 31);
-  const int qrow = (w % C::WQ) * (32 * C::NQB) + (lane & 31);
-  const int chunk = 2 * g + (lane >> 5);
+  const int prow = (w / C::WQ) * (C::BM * C::NPB) + (lane & 15);
+  const int qrow = (w % C::WQ) * (C::BM * C::NQB) + (lane & 15);
+  const int chunk = 4 * g + (lane >> 4);
 #pragma unroll
-  for (int i = 0; i < C::NPB; ++i) pf[i] = *reinterpret_cast<const u32x4*>(tp + lds_off(prow + 32 * i, chunk));
+  for (int i = 0; i < C::NPB; ++i) pf[i] = *reinterpret_cast<const u32x4*>(tp + lds_off(prow + C::BM * i, chunk));
 #pragma unroll
-  for (int j = 0; j < C::NQB; ++j) qf[j] = *reinterpret_cast<const u32x4*>(tq + lds_off(qrow + 32 * j, chunk));
+  for (int j = 0; j < C::NQB; ++j) qf[j] = *reinterpret_cast<const u32x4*>(tq + lds_off(qrow + C::BM * j, chunk));
 }
 
-// One K step (four groups of 16 k for bf16 / 8 k for fp32).  Fragments are
-// double-buffered in registers: the LDS reads of group g + 1 are issued before
-// the MFMAs of group g, and scheduling fences keep the compiler from sinking
+// One K step (two groups of 32 k for bf16 / 16 k for fp32).  Fragments are
+// double-buffered in registers: the LDS reads of group 1 are issued before
+// the MFMAs of group 0, and scheduling fences keep the compiler from sinking
 // them back next to their use.
 template <typename T, class C, class Acc>
 __device__ __forceinline__ void compute_stage(const char* tp, const char* tq, Acc& acc) {
   u32x4 pf[2][C::NPB], qf[2][C::NQB];
   load_frags<C>(tp, tq, 0, pf[0], qf[0]);
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {
+  for (int g = 0; g < 2; ++g) {
     const int cur = g & 1;
-    if (g < 3) load_frags<C>(tp, tq, g + 1, pf[cur ^ 1], qf[cur ^ 1]);
+    if (g < 1) load_frags<C>(tp, tq, g + 1, pf[cur ^ 1], qf[cur ^ 1]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < C::NPB; ++i)
@@ -196,7 +202,7 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
 #pragma unroll
   for (int i = 0; i < C::NPB; ++i)
 #pragma unroll
-    for (int j = 0; j < C::NQB; ++j) acc[i][j] = (f32x16){};
+    for (int j = 0; j < C::NQB; ++j) acc[i][j] = typename C::Frag{};
 }
 
 // nks steps over K.  hook(ks, acc) runs after step ks, past the barrier; it

@@ -123,27 +123,32 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z(const T* __restrict__ H, const T* __restr
   op.init(H + t0 * d, nullptr, (int)min<int64_t>(G::BP, rows - t0), ldb, (unsigned)ldb);
   DmaOp<G::NW, G::BQ, true> oq;
   oq.init(Wg + (int64_t)j0 * d, Wu + (int64_t)j0 * d, min(G::BQ / 2, f - j0), ldb, (unsigned)ldb);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
-  static_assert(G::NQB == 2, "one gate/up block pair per wave");
-  const int j = j0 + (wave_id() % G::WQ) * 32 + (lane_id() & 31);
-  if (j >= f) return;
+  // Each wave's 64 Q rows are 32 W_gate rows (blocks 0, 1) then the same 32
+  // W_up rows (blocks 2, 3): block jj pairs with block jj + 2.
+  static_assert(G::NQB == 4 && G::BM == 16, "two gate/up block pairs per wave");
 #pragma unroll
-  for (int i = 0; i < G::NPB; ++i) {
+  for (int jj = 0; jj < 2; ++jj) {
+    const int j = j0 + (wave_id() % G::WQ) * 32 + jj * 16 + (lane_id() & 15);
+    if (j >= f) continue;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int64_t row = t0 + G::acc_p(i, g);
-      if (row >= rows) continue;
-      float z[4];
+    for (int i = 0; i < G::NPB; ++i) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[e] = silu_f(acc[i][0][4 * g + e]) * acc[i][1][4 * g + e];
-      const int64_t b = row / n, t = row - b * n;
-      store4(Zt + (b * f + j) * (int64_t)n + t, z[0], z[1], z[2], z[3]);
-      if (Z != nullptr) {
+      for (int g = 0; g < G::GPB; ++g) {
+        const int64_t row = t0 + G::acc_p(i, g);
+        if (row >= rows) continue;
+        float z[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Z[(row + e) * f + j] = from_f32<T>(z[e]);
+        for (int e = 0; e < 4; ++e) z[e] = silu_f(acc[i][jj][4 * g + e]) * acc[i][jj + 2][4 * g + e];
+        const int64_t b = row / n, t = row - b * n;
+        store4(Zt + (b * f + j) * (int64_t)n + t, z[0], z[1], z[2], z[3]);
+        if (Z != nullptr) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Z[(row + e) * f + j] = from_f32<T>(z[e]);
+        }
       }
     }
   }
@@ -167,7 +172,7 @@ TTT_GEMM_KERNEL(Wide) void k_produce_vhat(const T* __restrict__ Y, const T* __re
   DmaOp<G::NW, G::BQ> oq;
   op.init(Y + t0 * d, nullptr, (int)min<int64_t>(G::BP, rows - t0), ldb, (unsigned)ldb);
   oq.init(WtT + (int64_t)o0 * d, nullptr, min(G::BQ, d - o0), ldb, (unsigned)ldb);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
@@ -178,7 +183,7 @@ TTT_GEMM_KERNEL(Wide) void k_produce_vhat(const T* __restrict__ Y, const T* __re
 #pragma unroll
     for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < G::GPB; ++g) {
         const int64_t row = t0 + G::acc_p(i, g);
         if (row >= rows) continue;
         const int64_t b = row / n, t = row - b * n;
@@ -200,16 +205,16 @@ __device__ __forceinline__ void for_state_quads(int j0, int i0, int d, int f, Fn
   const int pl = G::acc_p(0, 0), ql = G::acc_q(0);
 #pragma unroll
   for (int jb = 0; jb < G::NQB; ++jb) {
-    const int i = i0 + ql + jb * 32;
+    const int i = i0 + ql + jb * G::BM;
     const int64_t rowoff = (int64_t)i * f + j0 + pl;
 #pragma unroll
     for (int ib = 0; ib < G::NPB; ++ib) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dj = ib * 32 + g * 8;
+      for (int g = 0; g < G::GPB; ++g) {
+        const int dj = ib * G::BM + g * 8;
         if (full || (i < d && j0 + pl + dj < f)) fn(rowoff, dj, ib, jb, g);
       }
-      __builtin_amdgcn_sched_barrier(0);   // one 32x32 block at a time
+      if (((ib + 1) * G::GPB) % 4 == 0) __builtin_amdgcn_sched_barrier(0);   // four quads at a time
     }
   }
 }
@@ -217,7 +222,7 @@ __device__ __forceinline__ void for_state_quads(int j0, int i0, int d, int f, Fn
 template <class G, typename TO, class Acc>
 __device__ __forceinline__ void store_state(const Acc& acc, TO* __restrict__ out, int j0, int i0, int d, int f) {
   for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
-    const f32x16& blk = acc[ib][jb];
+    const auto& blk = acc[ib][jb];
     store4(out + ro + dj, blk[4 * g], blk[4 * g + 1], blk[4 * g + 2], blk[4 * g + 3]);
   });
 }
@@ -245,7 +250,7 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_delta(const T* __restrict__ Zt, const T* __re
   DmaOp<G::NW, G::BQ> oq;
   op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C_, nullptr, min(G::BP, f - j0), ldb, kbytes);
   oq.init(Vt + ((int64_t)b * d + i0) * n + (int64_t)c * C_, nullptr, min(G::BQ, d - i0), ldb, kbytes);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
   store_state<G>(acc, dW + (int64_t)bc * d * f, j0, i0, d, f);
@@ -317,7 +322,7 @@ TTT_GEMM_KERNEL(Narrow) void k_chunk_update_scan(const T* __restrict__ Zt, const
   DmaOp<G::NW, G::BQ> oq;
   op.init(Zt + ((int64_t)b * f + j0) * n, nullptr, min(G::BP, f - j0), ldb, (unsigned)ldb);
   oq.init(Vt + ((int64_t)b * d + i0) * n, nullptr, min(G::BQ, d - i0), ldb, (unsigned)ldb);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
     const f32x4 w = load4(W0 + ro + dj);
@@ -356,7 +361,7 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Z, const T* __restrict_
   op.init(W + (int64_t)b * wsb + (int64_t)c * wsc + (int64_t)i0 * f, nullptr, min(G::BP, d - i0), ldb,
           (unsigned)ldb);
   oq.init(Z + row0 * f, nullptr, min(G::BQ, C_ - t0), ldb, (unsigned)ldb);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
@@ -367,7 +372,7 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Z, const T* __restrict_
 #pragma unroll
     for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < G::GPB; ++g) {
         const int p = i0 + G::acc_p(i, g);
         if (full || (t0 + t < C_ && p < d))
           store4(O + (row0 + t) * d + p, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
@@ -401,7 +406,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Z, const T* __restr
   DmaOp<G::NW, G::BQ> oq;
   op.init(Z + (row0 + t0) * f, nullptr, min(G::BP, C_ - t0), ldb, (unsigned)ldb);
   oq.init(W + (int64_t)b * wsb + (int64_t)i0 * f, nullptr, min(G::BQ, d - i0), ldb, (unsigned)ldb);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
@@ -412,7 +417,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Z, const T* __restr
 #pragma unroll
     for (int ib = 0; ib < G::NPB; ++ib)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < G::GPB; ++g) {
         const int t = t0 + G::acc_p(ib, g);
         if (t >= C_) continue;
         float a[4];
@@ -450,7 +455,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __res
   op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C_, nullptr, min(G::BP, f - j0), (uint64_t)n * esz<T>(),
           kbytes);
   oq.init(Rt + ((int64_t)b * d + i0) * C_, nullptr, min(G::BQ, d - i0), (uint64_t)kbytes, kbytes);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
 

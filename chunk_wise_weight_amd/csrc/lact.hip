@@ -98,33 +98,39 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restr
   DmaOp<G::NW, G::BQ, true> oq;
   oq.init(W1s + bh * md + (int64_t)j0 * dh, W3s + bh * md + (int64_t)j0 * dh, min(G::BQ / 2, m - j0), ldb,
           (unsigned)ldb);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
-  const int j = j0 + (wave_id() % G::WQ) * 32 + (lane_id() & 31);
-  if (j >= m) return;
+  // Each wave's 64 Q rows are 32 W1 rows (blocks 0, 1) then the same 32 W3 rows
+  // (blocks 2, 3): block jj pairs with block jj + 2.
+  static_assert(G::NQB == 4 && G::BM == 16, "two W1/W3 block pairs per wave");
   T* hh = Hh + ((int64_t)part * BH + bh) * C * m;
-  const int64_t tb = ((int64_t)bh * m + j) * C;     // row j of the [BH, m, C] buffers
 #pragma unroll
-  for (int i = 0; i < G::NPB; ++i) {
+  for (int jj = 0; jj < 2; ++jj) {
+    const int j = j0 + (wave_id() % G::WQ) * 32 + jj * 16 + (lane_id() & 15);
+    if (j >= m) continue;
+    const int64_t tb = ((int64_t)bh * m + j) * C;     // row j of the [BH, m, C] buffers
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int r = r0 + G::acc_p(i, g);
-      if (r >= nrows) continue;
-      float a[4], u[4], h[4];
+    for (int i = 0; i < G::NPB; ++i) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = acc[i][0][4 * g + e];
-        u[e] = acc[i][1][4 * g + e];
-        h[e] = silu_f(a[e]) * u[e];
-      }
+      for (int g = 0; g < G::GPB; ++g) {
+        const int r = r0 + G::acc_p(i, g);
+        if (r >= nrows) continue;
+        float a[4], u[4], h[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) hh[(int64_t)(r + e) * m + j] = from_f32<T>(h[e]);
-      if (part) {
-        store4(HhT + tb + r, h[0], h[1], h[2], h[3]);
-        store4(At + tb + r, a[0], a[1], a[2], a[3]);
-        store4(Ut + tb + r, u[0], u[1], u[2], u[3]);
+        for (int e = 0; e < 4; ++e) {
+          a[e] = acc[i][jj][4 * g + e];
+          u[e] = acc[i][jj + 2][4 * g + e];
+          h[e] = silu_f(a[e]) * u[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hh[(int64_t)(r + e) * m + j] = from_f32<T>(h[e]);
+        if (part) {
+          store4(HhT + tb + r, h[0], h[1], h[2], h[3]);
+          store4(At + tb + r, a[0], a[1], a[2], a[3]);
+          store4(Ut + tb + r, u[0], u[1], u[2], u[3]);
+        }
       }
     }
   }
@@ -158,7 +164,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __rest
   DmaOp<G::NW, G::BQ> oq;
   op.init(W2s + (int64_t)bh * dh * m + (int64_t)i0 * m, nullptr, min(G::BP, dh - i0), ldb, (unsigned)ldb);
   oq.init(Hh + (((int64_t)part * BH + bh) * C + r0) * m, nullptr, min(G::BQ, nrows - r0), ldb, (unsigned)ldb);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
@@ -169,7 +175,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __rest
 #pragma unroll
     for (int ib = 0; ib < G::NPB; ++ib)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < G::GPB; ++g) {
         const int i = i0 + G::acc_p(ib, g);
         if (i >= dh) continue;
         float y[4];
@@ -212,7 +218,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_dh(const T* __restrict__ R, const T* __restric
   DmaOp<G::NW, G::BQ> oq;
   op.init(R + ((int64_t)bh * C + t0) * dh, nullptr, min(G::BP, nk - t0), ldb, (unsigned)ldb);
   oq.init(W2Ts + (int64_t)bh * m * dh + (int64_t)j0 * dh, nullptr, min(G::BQ, m - j0), ldb, (unsigned)ldb);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
@@ -224,7 +230,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_dh(const T* __restrict__ R, const T* __restric
 #pragma unroll
     for (int ib = 0; ib < G::NPB; ++ib)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < G::GPB; ++g) {
         const int t = t0 + G::acc_p(ib, g);
         if (t >= nk) continue;
         const f32x4 a = load4(At + rowj + t), u = load4(Ut + rowj + t);
@@ -290,7 +296,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_grad(const T* __restrict__ Kt, const T* __rest
   DmaOp<G::NW, G::BQ> oq;
   op.init(Pbase, nullptr, min(G::BP, PD - p0), pld, kbytes);
   oq.init(Qbase, nullptr, min(G::BQ, QD - q0), qld, kbytes);
-  f32x16 acc[G::NPB][G::NQB];
+  typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
 
@@ -303,7 +309,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_grad(const T* __restrict__ Kt, const T* __rest
 #pragma unroll
     for (int ib = 0; ib < G::NPB; ++ib)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < G::GPB; ++g) {
         const int pi = p0 + G::acc_p(ib, g);
         if (pi < PD)
           store4(out + (int64_t)qi * PD + pi, acc[ib][jq][4 * g], acc[ib][jq][4 * g + 1], acc[ib][jq][4 * g + 2],
