@@ -107,6 +107,7 @@ def bench_inplace_dot(cfg, steps, warmup):
     O = torch.empty(B, n, d, dtype=dt, device="cuda")
     shape = cw.InplaceShape(B, n, d, f, C, cfg.conv_k)
     vws = torch.empty(cw.ttt_vhat_workspace_bytes(shape, dt), dtype=torch.uint8, device="cuda")
+    uws = torch.empty(max(1, cw.ttt_update_scan_workspace_bytes(shape, dt)), dtype=torch.uint8, device="cuda")
     names = ["produce_z", "produce_vhat", "update_scan", "apply"]
 
     def step(ev=None):
@@ -115,7 +116,7 @@ def bench_inplace_dot(cfg, steps, warmup):
         if ev: ev[1].record()
         cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"], Vt, vws, scale=cfg.eta)
         if ev: ev[2].record()
-        cw.ttt_chunk_update_scan(Zt, Vt, g["W_down0"], C, Wc, Wf)
+        cw.ttt_chunk_update_scan(Zt, Vt, g["W_down0"], C, Wc, Wf, uws)
         if ev: ev[3].record()
         cw.ttt_chunk_apply(Z, Wc, C, O)
         if ev: ev[4].record()

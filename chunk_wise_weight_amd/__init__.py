@@ -16,7 +16,7 @@ from ._lib import (  # noqa: F401
     TTT_ERR_UNSUPPORTED, TTT_F32, TTT_BF16, TTT_MODE_DOT, TTT_MODE_MSE, TTT_MODE_DOT_SCAN,
     TTT_UPDATE_THEN_APPLY, TTT_APPLY_THEN_UPDATE, TTTError, InplaceShape, LactShape,
     lib, lib_path, exported_symbols, status_string,
-    ttt_inplace_workspace_bytes, ttt_lact_workspace_bytes, ttt_vhat_workspace_bytes,
+    ttt_inplace_workspace_bytes, ttt_lact_workspace_bytes, ttt_vhat_workspace_bytes, ttt_update_scan_workspace_bytes,
     ttt_chunk_apply_update, ttt_core_apply_update, ttt_produce_z, ttt_produce_vhat,
     ttt_chunk_delta, ttt_chunk_scan, ttt_chunk_update_scan, ttt_chunk_apply, ttt_lact_swiglu,
 )

@@ -51,7 +51,8 @@ _SIGNATURES = {
     "ttt_produce_vhat": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _S, _P]),
     "ttt_chunk_delta": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P]),
     "ttt_chunk_scan": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P]),
-    "ttt_chunk_update_scan": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P, _P]),
+    "ttt_update_scan_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, ctypes.POINTER(_S)]),
+    "ttt_chunk_update_scan": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P, _P, _S, _P]),
     "ttt_chunk_apply": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P]),
     "ttt_lact_workspace_bytes": (_I, [ctypes.POINTER(LactShape), _I, ctypes.POINTER(_S)]),
     "ttt_lact_swiglu": (_I, [ctypes.POINTER(LactShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -268,7 +269,14 @@ def ttt_chunk_scan(dW, W_down0, eta: float, chunk: int, seq_len: int, Wc=None, W
     return Wc, W_final
 
 
-def ttt_chunk_update_scan(Zt, Vt, W_down0, chunk: int, Wc=None, W_final=None):
+def ttt_update_scan_workspace_bytes(shape: InplaceShape, dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().ttt_update_scan_workspace_bytes(ctypes.byref(shape), _dt(dtype), ctypes.byref(out)),
+           "ttt_update_scan_workspace_bytes")
+    return out.value
+
+
+def ttt_chunk_update_scan(Zt, Vt, W_down0, chunk: int, Wc=None, W_final=None, workspace=None):
     """Fused deltas + prefix from Zt [B, f, n] and the eta-scaled target Vt [B, d, n] (ttt_produce_vhat with
     scale = eta).  Returns (Wc [B, k, d, f] dtype, W_final fp32)."""
     B, f, n = Zt.shape
@@ -283,8 +291,12 @@ def ttt_chunk_update_scan(Zt, Vt, W_down0, chunk: int, Wc=None, W_final=None):
     _need(Wc, "Wc", (B, k, d, f), dt, dev)
     _need(W_final, "W_final", (B, d, f), torch.float32, dev)
     shape = _inplace_shape(B, n, d, f, chunk, 1)
+    need = ttt_update_scan_workspace_bytes(shape, dt) if B * n > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().ttt_chunk_update_scan(ctypes.byref(shape), _dt(dt), _ptr(W_down0), _ptr(Zt), _ptr(Vt), _ptr(Wc),
-                                       _ptr(W_final), _stream(dev)), "ttt_chunk_update_scan")
+                                       _ptr(W_final), _ptr(workspace), wsb, _stream(dev)), "ttt_chunk_update_scan")
     return Wc, W_final
 
 

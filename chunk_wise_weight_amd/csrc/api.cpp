@@ -24,8 +24,9 @@ struct Plan {
   int64_t B, n, d, f, C, K, k;
   size_t esz;
   bool fused;
+  int S;              // sequence segments of the fused update-scan
   // workspace regions (byte offsets); Z, Y and WtT only with the producers
-  size_t off_Z, off_Y, off_WtT, off_Zt, off_Vt, off_Wc, off_dW, off_Rt, off_Wsh, total;
+  size_t off_Z, off_Y, off_WtT, off_Zt, off_Vt, off_Wc, off_dW, off_Wp, off_Tot, off_Rt, off_Wsh, total;
 };
 
 int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
@@ -62,7 +63,9 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   p->fused = mode == TTT_MODE_DOT && p->C % kstep(dtype) == 0;
   const size_t BN = (size_t)p->B * p->n, DF = (size_t)p->d * p->f;
   size_t off = 0;
-  p->off_Z = p->off_Y = p->off_WtT = p->off_Zt = p->off_Vt = p->off_Wc = p->off_dW = p->off_Rt = p->off_Wsh = 0;
+  p->S = p->fused ? ttt::update_scan_segments(p->d, p->f, p->k) : 1;
+  p->off_Z = p->off_Y = p->off_WtT = p->off_Zt = p->off_Vt = p->off_Wc = p->off_dW = p->off_Wp = p->off_Tot = 0;
+  p->off_Rt = p->off_Wsh = 0;
   if (producers) {
     p->off_Z = off;
     off += align_up(BN * p->f * p->esz);
@@ -81,6 +84,11 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
     if (!p->fused) {
       p->off_dW = off;
       off += align_up((size_t)p->B * p->k * DF * 4);
+    } else if (p->S > 1) {
+      p->off_Wp = off;
+      off += align_up((size_t)p->B * (p->k - p->k / p->S) * DF * 4);
+      p->off_Tot = off;
+      off += align_up((size_t)p->B * (p->S - 1) * DF * 4);
     }
   } else {
     p->off_Rt = off;
@@ -136,7 +144,8 @@ int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Ztv
   T* Wc = (T*)(ws + p.off_Wc);
   int st;
   if (p.fused) {
-    st = dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, B, n, d, f, C, s));   // Vt carries eta
+    st = dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (float*)(ws + p.off_Wp), (float*)(ws + p.off_Tot),
+                                              B, n, d, f, C, p.S, s));   // Vt carries eta
   } else {
     float* dW = (float*)(ws + p.off_dW);
     st = dev(ttt::launch_chunk_delta<T>(Zt, Vt, dW, B, n, d, f, C, s));
@@ -357,8 +366,26 @@ int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const v
                                            eta, s));
 }
 
+static size_t update_scan_ws(const ttt_inplace_shape* s) {
+  const int64_t k = s->seq_len / s->chunk;
+  const int S = ttt::update_scan_segments(s->d_model, s->d_ff, k);
+  if (S == 1) return 0;
+  const size_t DF = (size_t)s->d_model * s->d_ff;
+  return align_up((size_t)s->batch * (k - k / S) * DF * 4) + align_up((size_t)s->batch * (S - 1) * DF * 4);
+}
+
+int ttt_update_scan_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_ARG;
+  int st = check_inplace_shape(shape, dtype);
+  if (st != TTT_OK) return st;
+  if (shape->chunk % kstep(dtype) != 0) return TTT_ERR_UNSUPPORTED;
+  *bytes = update_scan_ws(shape);
+  return TTT_OK;
+}
+
 int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void* W_down0, const void* Zt,
-                          const void* Vt, void* Wc, float* W_final, void* stream) {
+                          const void* Vt, void* Wc, float* W_final, void* workspace, size_t workspace_bytes,
+                          void* stream) {
   int st = check_inplace_shape(shape, dtype);
   if (st != TTT_OK) return st;
   if (shape->chunk % kstep(dtype) != 0) return TTT_ERR_UNSUPPORTED;
@@ -374,11 +401,17 @@ int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void*
     return dev(ttt::launch_chunk_scan<float>(nullptr, (const float*)W_down0, nullptr, W_final, B, 0, df, 0.f, s));
   }
   if (!ok_ptr(Zt) || !ok_ptr(Vt) || !ok_ptr(Wc)) return TTT_ERR_ARG;
+  const size_t need = update_scan_ws(shape);
+  if (workspace_bytes < need || (need > 0 && !ok_ptr(workspace))) return TTT_ERR_WORKSPACE;
+  const int k = n / C, S = ttt::update_scan_segments(d, f, k);
+  char* ws = (char*)workspace;
+  float* Wp = S > 1 ? (float*)ws : nullptr;
+  float* Tot = S > 1 ? (float*)(ws + align_up((size_t)B * (k - k / S) * df * 4)) : nullptr;
   if (dtype == TTT_BF16)
     return dev(ttt::launch_chunk_update_scan<bf16>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)W_down0, (bf16*)Wc,
-                                                   W_final, B, n, d, f, C, s));
+                                                   W_final, Wp, Tot, B, n, d, f, C, S, s));
   return dev(ttt::launch_chunk_update_scan<float>((const float*)Zt, (const float*)Vt, (const float*)W_down0,
-                                                  (float*)Wc, W_final, B, n, d, f, C, s));
+                                                  (float*)Wc, W_final, Wp, Tot, B, n, d, f, C, S, s));
 }
 
 int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Wc, void* O, void* stream) {

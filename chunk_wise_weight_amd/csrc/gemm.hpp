@@ -4,12 +4,10 @@
 // sum_k P[p][k] * Q[q][k] and walks K in steps of 128 bytes (64 bf16 or 32
 // fp32).  Both operands are K-contiguous in global memory.  Wave (wp, wq)
 // owns NPB x NQB 16x16 MFMA accumulator blocks (BP = 16 NPB WP,
-// BQ = 16 NQB WQ).  Two shapes are used:
-//   Wide   = 8 waves, 2 x 4, 8 x 4 blocks: 256 x 256 tile, 128 accumulators
-//            per lane, two waves per SIMD so that one wave's LDS and barrier
-//            waits are covered by the other's MFMAs;
-//   Narrow = 4 waves, 2 x 2, 8 x 4 blocks: 256 x 128 tile, for grids where a
-//            256 x 256 tiling would leave most of a wave of workgroups idle.
+// BQ = 16 NQB WQ).  Every kernel uses one shape:
+//   Wide = 8 waves, 2 x 4, 8 x 4 blocks: 256 x 256 tile, 128 accumulators per
+//          lane, two waves per SIMD so that one wave's LDS and barrier waits
+//          are covered by the other's MFMAs.
 //
 // Global -> LDS: buffer_load_dwordx4 ... lds (LDS DMA).  One instruction moves
 // 64 lanes x 16 B = 8 rows x 128 B of a tile with no VGPR staging.  Out-of-range
@@ -63,7 +61,6 @@ struct TileCfg {
   __device__ static __forceinline__ int acc_q(int j) { return (wave_id() % WQ) * (BM * NQB) + j * BM + (lane_id() & 15); }
 };
 using Wide = TileCfg<2, 4, 8, 4>;
-using Narrow = TileCfg<2, 2, 8, 4>;
 
 // Kernel attributes: NT threads, and the number of waves per SIMD the register
 // budget is planned for (the scheduler then spends registers on keeping LDS

@@ -278,61 +278,108 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW
          fmaf(eta, s[3], w0[3]));
 }
 
-// Fused delta + scan: each workgroup owns one [256 d_ff x 128 d_model] tile of
-// the state and runs its K loop over the whole sequence in token order.  The
-// accumulator starts at W_down0 and the target arrives pre-scaled by eta
-// (Vt = eta V^^T: eta times a delta equals the delta of eta times the target),
-// so after the tokens of chunks 0..c-1 it holds exactly W_c, the state chunk c
-// is applied with.  At each chunk boundary the tile is stored in the operand
-// dtype; after the last chunk in fp32 as W_final.  The narrow tile keeps the
-// accumulator at 128 registers per lane, which leaves room for the snapshot
-// stores inside the K loop, and gives 760 tiles at d = 2560, f = 9728.
+// Fused delta + scan.  The per-chunk delta does not depend on the state, so
+// W_c = W_down0 + sum_{j<c} (eta V^_j)^T Z_j is the running value of ONE
+// contraction over the tokens, read out at every chunk boundary: each
+// workgroup owns one 256 x 256 tile of the state and runs its K loop in token
+// order.  The target arrives pre-scaled by eta (eta times a delta is the delta
+// of eta times the target), so the accumulator holds exactly the state.
+//
+// To fill the chip when the state has few tiles, the sequence is cut into S
+// segments of k / S chunks that run side by side.  Segment 0 starts from
+// W_down0 and writes the states W_c of its chunks in the operand dtype; a
+// later segment starts from zero and writes fp32 partial states to Wp
+// (chunks after its first) and its total to Tot[b, s - 1] -- except the last
+// segment, whose total goes to W_final.  k_scan_fixup then adds the earlier
+// segments' totals.  With S = 1 the kernel alone produces every output.
 template <typename T>
 struct SnapshotHook {
-  T* Wc;              // [k, d, f] of this batch row
-  int steps_per_chunk, k, j0, i0, d, f;
+  T* Wc;              // [k, d, f] states of this batch row (segment 0)
+  float* Wp;          // partial states of this batch row; chunk c at Wp + (c - kS) d f (later segments)
+  int steps_per_chunk, c0, c1, kS, j0, i0, d, f;
   template <class A>
   __device__ __forceinline__ void operator()(int ks, A& acc) const {
     const int done = ks + 1;
     if (done % steps_per_chunk != 0) return;
-    const int c = done / steps_per_chunk;
-    if (c >= k) return;
-    store_state<Narrow>(acc, Wc + (int64_t)c * d * f, j0, i0, d, f);
+    const int c = c0 + done / steps_per_chunk;
+    if (c >= c1) return;
+    const int64_t df = (int64_t)d * f;
+    if (c0 == 0)
+      store_state<Wide>(acc, Wc + (int64_t)c * df, j0, i0, d, f);
+    else
+      store_state<Wide>(acc, Wp + (int64_t)(c - kS) * df, j0, i0, d, f);
   }
 };
 
 template <typename T>
-TTT_GEMM_KERNEL(Narrow) void k_chunk_update_scan(const T* __restrict__ Zt, const T* __restrict__ Vt,
-                                                 const T* __restrict__ W0, T* __restrict__ Wc, float* __restrict__ Wf,
-                                                 int n, int d, int f, int C_) {
-  using G = Narrow;
+TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T* __restrict__ Vt,
+                                               const T* __restrict__ W0, T* __restrict__ Wc, float* __restrict__ Wp,
+                                               float* __restrict__ Tot, float* __restrict__ Wf, int n, int d, int f,
+                                               int C_, int S) {
+  using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (f + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int b = id / per;
+  const int bs = id / per;
+  const int b = bs / S, sg = bs - b * S;
   int tp, tq;
-  grouped_tile(id - b * per, TP, TQ, 4, tp, tq);
-  const int k = n / C_;
+  grouped_tile(id - bs * per, TP, TQ, 4, tp, tq);
+  const int k = n / C_, kS = k / S;
+  const int c0 = sg * kS;
   const int j0 = tp * G::BP, i0 = tq * G::BQ;
+  const int64_t df = (int64_t)d * f;
   const uint64_t ldb = (uint64_t)n * esz<T>();
-  T* wc = Wc + (int64_t)b * k * d * f;
+  const unsigned kbytes = (unsigned)kS * C_ * esz<T>();
 
   DmaOp<G::NW, G::BP> op;
   DmaOp<G::NW, G::BQ> oq;
-  op.init(Zt + ((int64_t)b * f + j0) * n, nullptr, min(G::BP, f - j0), ldb, (unsigned)ldb);
-  oq.init(Vt + ((int64_t)b * d + i0) * n, nullptr, min(G::BQ, d - i0), ldb, (unsigned)ldb);
+  op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c0 * C_, nullptr, min(G::BP, f - j0), ldb, kbytes);
+  oq.init(Vt + ((int64_t)b * d + i0) * n + (int64_t)c0 * C_, nullptr, min(G::BQ, d - i0), ldb, kbytes);
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
-  for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
-    const f32x4 w = load4(W0 + ro + dj);
+  T* wc = Wc + (int64_t)b * k * df;
+  if (sg == 0) {
+    for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+      const f32x4 w = load4(W0 + ro + dj);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
-  });
-  store_state<G>(acc, wc, j0, i0, d, f);                                  // chunk 0: W_down0
-  const SnapshotHook<T> hook{wc, C_ * esz<T>() / 128, k, j0, i0, d, f};
-  mainloop<T, G>(op, oq, (int)(ldb / 128), acc, smem, hook);
-  store_state<G>(acc, Wf + (int64_t)b * d * f, j0, i0, d, f);            // after the last chunk
+      for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
+    });
+    store_state<G>(acc, wc, j0, i0, d, f);                                // chunk 0: W_down0
+  }
+  const SnapshotHook<T> hook{wc, Wp + (int64_t)b * (k - kS) * df, C_ * esz<T>() / 128, c0, c0 + kS, kS,
+                             j0, i0, d, f};
+  mainloop<T, G>(op, oq, (int)(kbytes / 128), acc, smem, hook);
+  float* out = sg == S - 1 ? Wf + (int64_t)b * df : Tot + ((int64_t)b * (S - 1) + sg) * df;
+  store_state<G>(acc, out, j0, i0, d, f);
+}
+
+// Completes a segmented update-scan: adds to every partial state of segments
+// 1..S-1, and to W_final, the total of the segments before it, rounding each
+// state once to the operand dtype.  Four elements per thread, grid.y = batch.
+template <typename T>
+__global__ __launch_bounds__(256) void k_scan_fixup(T* __restrict__ Wc, const float* __restrict__ Wp,
+                                                    const float* __restrict__ Tot, float* __restrict__ Wf, int k,
+                                                    int S, int64_t df) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= df) return;
+  const int b = blockIdx.y, kS = k / S;
+  T* wc = Wc + (int64_t)b * k * df + e;
+  const float* wp = Wp + (int64_t)b * (k - kS) * df + e;
+  const float* tot = Tot + (int64_t)b * (S - 1) * df + e;
+  f32x4 off = load4(tot);                                   // W_down0 + segment 0
+  for (int sg = 1; sg < S; ++sg) {
+    const int c0 = sg * kS;
+    store4(wc + (int64_t)c0 * df, off[0], off[1], off[2], off[3]);
+    for (int c = c0 + 1; c < c0 + kS; ++c) {
+      const f32x4 pv = load4(wp + (int64_t)(c - kS) * df);
+      store4(wc + (int64_t)c * df, off[0] + pv[0], off[1] + pv[1], off[2] + pv[2], off[3] + pv[3]);
+    }
+    if (sg < S - 1) off += load4(tot + (int64_t)sg * df);
+  }
+  float* wf = Wf + (int64_t)b * df + e;
+  const f32x4 w = load4(wf);
+  store4(wf, w[0] + off[0], w[1] + off[1], w[2] + off[2], w[3] + off[3]);
 }
 
 // ------------------------------------------------------------------ apply
@@ -476,7 +523,6 @@ TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __res
 
 static inline unsigned tiles_u(int64_t t) { return (unsigned)t; }
 constexpr int kWB = Wide::BP;       // 256 x 256 tiles
-constexpr int kNP = Narrow::BP, kNQ = Narrow::BQ;
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <typename T>
@@ -533,11 +579,15 @@ hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int
 }
 
 template <typename T>
-hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, int B, int n, int d,
-                                    int f, int Cs, hipStream_t s) {
-  const int64_t tiles = cdiv(f, kNP) * cdiv(d, kNQ) * B;
+hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, float* Wp, float* Tot,
+                                    int B, int n, int d, int f, int Cs, int S, hipStream_t s) {
+  const int64_t tiles = cdiv(f, kWB) * cdiv(d, kWB) * B * S;
   if (tiles == 0) return hipSuccess;
-  k_chunk_update_scan<T><<<tiles_u(tiles), Narrow::NT, 0, s>>>(Zt, Vt, W0, Wc, Wf, n, d, f, Cs);
+  k_chunk_update_scan<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f, Cs, S);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  const int64_t df = (int64_t)d * f;
+  k_scan_fixup<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(Wc, Wp, Tot, Wf, n / Cs, S, df);
   return hipGetLastError();
 }
 
@@ -574,8 +624,8 @@ hipError_t launch_mse_chunk(const T* Z, const T* Zt, const T* Vt, const T* W0, c
   template hipError_t launch_chunk_delta<T>(const T*, const T*, float*, int, int, int, int, int, hipStream_t);   \
   template hipError_t launch_chunk_scan<T>(const float*, const T*, T*, float*, int, int, int64_t, float,         \
                                            hipStream_t);                                                          \
-  template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, int, int, int, int,  \
-                                                  int, hipStream_t);                                              \
+  template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, float*, float*, int,  \
+                                                  int, int, int, int, int, hipStream_t);                          \
   template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int,          \
                                       hipStream_t);                                                               \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, const T*, float*, T*, T*, T*,   \

@@ -24,8 +24,22 @@ template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
                              hipStream_t s);
 template <typename T>
-hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, int B, int n, int d,
-                                    int f, int C, hipStream_t s);
+hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, float* Wp, float* Tot,
+                                    int B, int n, int d, int f, int C, int S, hipStream_t s);
+
+// Number of sequence segments the fused update-scan runs side by side: more
+// than one only when it fills the 256 compute units markedly better with one
+// batch row (a segment count must divide the chunk count).  It depends on the
+// state's shape alone, so a batch row's summation order, and with it every
+// bit of its result, does not depend on the other rows of the batch.
+inline int update_scan_segments(int64_t d, int64_t f, int64_t k) {
+  const int64_t tiles = ((f + 255) / 256) * ((d + 255) / 256);
+  auto fill = [](int64_t t) { return t == 0 ? 1.0 : (double)t / (256.0 * (double)((t + 255) / 256)); };
+  int S = 1;
+  for (int cand : {2, 4})
+    if (k % cand == 0 && fill(tiles * cand) > fill(tiles * S) + 0.05) S = cand;
+  return S;
+}
 template <typename T>
 hipError_t launch_apply(const T* Z, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
                         hipStream_t s);

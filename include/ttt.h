@@ -162,16 +162,27 @@ int ttt_chunk_delta(const ttt_inplace_shape* shape, int dtype, const void* Zt, c
 int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const void* W_down0,
                    const float* dW, void* Wc, float* W_final, void* stream);
 
+/* Scratch of ttt_chunk_update_scan for these sizes: 0 when the sequence runs
+ * as one segment, else the fp32 partial states and segment totals below. */
+int ttt_update_scan_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes);
+
 /* Deltas and scan fused (chunk % 64 == 0 for bf16, % 32 for fp32, else
  * TTT_ERR_UNSUPPORTED), with eta carried by the target: Vt = eta * V^^T (from
  * ttt_produce_vhat with scale = eta), since eta V^_c^T Z_c = (eta V^_c)^T Z_c.
- * One MFMA pass over the sequence per output tile, whose fp32 accumulator
- * starts at W_down0 and so holds W_c after the tokens of chunks 0..c-1; at
- * each chunk boundary the tile writes Wc[b, c], after the last chunk W_final.
+ * The deltas do not depend on the state (eq. (6)), so the scan is the running
+ * value of one contraction over the tokens: one MFMA pass per output tile,
+ * whose fp32 accumulator starts at W_down0 and holds W_c after the tokens of
+ * chunks 0..c-1; at each chunk boundary the tile writes Wc[b, c], after the
+ * last chunk W_final.  When the state has too few tiles to fill the GPU, the
+ * sequence runs as S side-by-side segments and a short elementwise pass adds
+ * the earlier segments' totals (fp32) before the single rounding to dtype;
+ * `workspace` (device, at least ttt_update_scan_workspace_bytes) holds the
+ * partial states and may be NULL when that query returns 0.
  * Same outputs as ttt_chunk_delta (on the unscaled target) followed by
  * ttt_chunk_scan with eta, without dW. */
-int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void* W_down0,
-                          const void* Zt, const void* Vt, void* Wc, float* W_final, void* stream);
+int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void* W_down0, const void* Zt,
+                          const void* Vt, void* Wc, float* W_final, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* Apply (eq. (3)): O [B, n, d], O_c = Z_c Wc[b, c]^T with Z [B, n, f] and
  * Wc [B, k, d, f] dtype. */

@@ -68,6 +68,47 @@ def test_workspace_sizes():
     assert out.value == al(n * d * 2) + al(d * d * 2)
 
 
+def _update_scan_ws(shape, dtype=cw.TTT_BF16):
+    out = ctypes.c_size_t(0)
+    st = cw.lib().ttt_update_scan_workspace_bytes(ctypes.byref(shape), dtype, ctypes.byref(out))
+    return st, out.value
+
+
+def test_update_scan_segments_and_workspace():
+    """The fused update-scan runs the sequence as S segments when that fills the 256 compute units
+    markedly better for one batch row (S depends on the state's shape only, so rows do not depend on
+    the batch they are in); its scratch holds the fp32 partial states of chunks past the first
+    segment and the S - 1 segment totals."""
+    al = lambda x: (x + 255) // 256 * 256
+
+    def expect(B, n, d, f, C):
+        k = n // C
+        tiles = -(-f // 256) * -(-d // 256)
+        fill = lambda t: t / (256 * -(-t // 256))
+        S = 1
+        for cand in (2, 4):
+            if k % cand == 0 and fill(tiles * cand) > fill(tiles * S) + 0.05:
+                S = cand
+        return S, (0 if S == 1 else al(B * (k - k // S) * d * f * 4) + al(B * (S - 1) * d * f * 4))
+
+    cases = [(1, 131072, 2560, 9728, 4096, 2), (1, 32768, 2560, 9728, 1024, 2), (1, 2048, 1024, 4096, 256, 4),
+             (2, 1024, 1024, 4096, 128, 4), (1, 2048, 256, 512, 256, 1), (4, 65536, 2048, 8192, 2048, 1),
+             (1, 4096, 2560, 9728, 4096, 1)]     # one chunk: nothing to split
+    for B, n, d, f, C, S in cases:
+        s_exp, ws = expect(B, n, d, f, C)
+        assert s_exp == S, (B, n, d, f, C)
+        st, nb = _update_scan_ws(cw.InplaceShape(B, n, d, f, C, 4))
+        assert st == cw.TTT_OK and nb == ws, (B, n, d, f, C)
+    # the layer's workspace carries the same regions in the fused dot plan
+    s = cw.InplaceShape(1, 2048, 1024, 4096, 256, 4)
+    st_seg, nb_seg = _ws(s, cw.TTT_BF16, cw.TTT_MODE_DOT, 0)
+    B, n, d, f, k = 1, 2048, 1024, 4096, 8
+    core = al(B * n * f * 2) + al(B * n * d * 2)
+    assert st_seg == cw.TTT_OK and nb_seg == core + al(B * k * d * f * 2) + _update_scan_ws(s)[1]
+    assert _update_scan_ws(cw.InplaceShape(1, 2048, 256, 512, 32, 4))[0] == cw.TTT_ERR_UNSUPPORTED
+    assert cw.lib().ttt_update_scan_workspace_bytes(ctypes.byref(s), cw.TTT_BF16, None) == cw.TTT_ERR_ARG
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(n=2000, C=256), cw.TTT_ERR_SHAPE),      # seq_len % chunk != 0
     (dict(C=0), cw.TTT_ERR_SHAPE),
@@ -135,8 +176,12 @@ def test_step_entry_points_validate():
     assert lib.ttt_chunk_delta(ctypes.byref(_shape(n=100)), cw.TTT_BF16, *[_fake()] * 3, None) == cw.TTT_ERR_SHAPE
     assert lib.ttt_chunk_scan(ctypes.byref(s), cw.TTT_BF16, float("inf"), *[_fake()] * 4, None) == cw.TTT_ERR_ARG
     # the fused update-scan needs chunk boundaries on 64-token steps in bf16
-    assert lib.ttt_chunk_update_scan(ctypes.byref(_shape(n=2048, C=32)), cw.TTT_BF16, *[_fake()] * 5, None) == \
+    assert lib.ttt_chunk_update_scan(ctypes.byref(_shape(n=2048, C=32)), cw.TTT_BF16, *[_fake()] * 6, 0, None) == \
         cw.TTT_ERR_UNSUPPORTED
+    # a segmented shape needs its scratch
+    seg = cw.InplaceShape(1, 2048, 1024, 4096, 256, 4)
+    assert lib.ttt_chunk_update_scan(ctypes.byref(seg), cw.TTT_BF16, *[_fake()] * 5, None, 0, None) == \
+        cw.TTT_ERR_WORKSPACE
     assert lib.ttt_chunk_apply(ctypes.byref(s), cw.TTT_BF16, _fake(), None, _fake(), None) == cw.TTT_ERR_ARG
 
 

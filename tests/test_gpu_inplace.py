@@ -126,6 +126,43 @@ def test_fused_update_scan_matches_materialised(dtype):
     assert torch.equal(Wc1[:, 0], Wg.expand(B, d, f))      # chunk 0 is applied with W_down0
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,n,d,f,C,segments", [
+    (1, 2048, 1024, 4096, 256, 4),     # 64 state tiles: four sequence segments
+    (2, 1024, 1024, 4096, 128, 4),     # two batch rows of 64 tiles: four segments each
+    (1, 1024, 2560, 2560, 256, 2),     # 100 tiles: two segments
+])
+def test_segmented_update_scan(dtype, B, n, d, f, C, segments):
+    """The fused update-scan cut into sequence segments (plus the fix-up pass) equals the materialised
+    deltas + scan and the oracle's prefix form; the partial states of later segments receive the
+    earlier segments' totals."""
+    shape = cw.InplaceShape(B, n, d, f, C, 1)
+    k = n // C
+    DF = d * f
+    al = lambda x: (x + 255) // 256 * 256
+    want_ws = al(B * (k - k // segments) * DF * 4) + al(B * (segments - 1) * DF * 4)
+    assert cw.ttt_update_scan_workspace_bytes(shape, torch.bfloat16 if dtype == "bf16" else torch.float32) == want_ws
+    eta = 0.02
+    Z, V, W0 = _zv(dtype, B, n, d, f, 31)
+    dt = Z.dtype
+    Vs = (V.double() * eta).to(dt)
+    Zt, Wg = _t(Z).cuda(), W0.cuda()
+    Wc1, Wf1 = cw.ttt_chunk_update_scan(Zt, _t(Vs).cuda(), Wg, C)
+    Wc2, Wf2 = cw.ttt_chunk_scan(cw.ttt_chunk_delta(Zt, _t(V).cuda(), C), Wg, eta, C, n)
+    torch.cuda.synchronize()
+    assert rel(f64(Wc1), f64(Wc2)) < STEP_TOL[dtype]
+    assert rel(f64(Wf1), f64(Wf2)) < STEP_TOL[dtype]
+    Zn, Vsn, W0n = f64(Z), f64(Vs), f64(W0)
+    for b in range(B):
+        _, Wref = orc.chunk_prefix_form(Zn[b], Vsn[b], W0n, C, 1.0)
+        assert rel(f64(Wf1[b]) - W0n, Wref - W0n) < 1e-5
+        # every chunk's state, segment starts included
+        Wcs = f64(Wc1[b])
+        for c in range(k):
+            _, Wc_ref = orc.chunk_prefix_form(Zn[b, : c * C], Vsn[b, : c * C], W0n, C, 1.0) if c else (None, W0n)
+            assert rel(Wcs[c], Wc_ref) < STEP_TOL[dtype], (b, c)
+
+
 # ---------------------------------------------------------------- whole layer
 
 def run_layer(cfg, mode=None):
