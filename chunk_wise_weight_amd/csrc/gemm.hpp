@@ -230,4 +230,43 @@ __device__ __forceinline__ void mainloop(const OP& op, const OQ& oq, int nks, Ac
 #endif
 }
 
+// ---------------------------------------------------------------- LDS-staged output
+
+// After the K loop the operand stages are free.  An output tile is assembled
+// there and copied out in whole 16-byte pieces along its rows, so that global
+// stores cover full cache lines rather than the 32-byte runs one lane's
+// accumulators map to.  Rows of COLS elements; piece c of row r sits at slot
+// c ^ (r & 15), which spreads the column-wise puts of 16 consecutive rows
+// over different banks.
+template <typename TO, int COLS>
+struct Staged {
+  static constexpr int RB = COLS * (int)sizeof(TO);     // bytes per row
+  static constexpr int PPR = RB / 16;                   // 16-byte pieces per row
+  static constexpr int EPP = 16 / (int)sizeof(TO);      // elements per piece
+  static_assert(PPR % 16 == 0, "rows of at least 16 pieces");
+  char* base;
+
+  __device__ __forceinline__ int off(int r, int col) const {
+    const int byte = col * (int)sizeof(TO);
+    return r * RB + ((((byte >> 4) ^ (r & 15))) << 4) + (byte & 15);
+  }
+  // elements col..col+3 of row r (col % 4 == 0: they share one piece)
+  __device__ __forceinline__ void put4(int r, int col, float a, float b, float c, float d) const {
+    store4(reinterpret_cast<TO*>(base + off(r, col)), a, b, c, d);
+  }
+  __device__ __forceinline__ void put1(int r, int col, float v) const {
+    *reinterpret_cast<TO*>(base + off(r, col)) = from_f32<TO>(v);
+  }
+  // Rows [0, nrows) out to global memory; dst(r, col) is the address of element
+  // col of row r (col a multiple of EPP, 16-byte aligned) or nullptr to skip.
+  template <int NT, class Dst>
+  __device__ __forceinline__ void flush(int nrows, Dst&& dst) const {
+    for (int idx = threadIdx.x; idx < nrows * PPR; idx += NT) {
+      const int r = idx / PPR, c = idx - r * PPR;
+      TO* p = dst(r, c * EPP);
+      if (p != nullptr) *reinterpret_cast<u32x4*>(p) = *reinterpret_cast<const u32x4*>(base + r * RB + ((c ^ (r & 15)) << 4));
+    }
+  }
+};
+
 }  // namespace ttt

@@ -114,7 +114,10 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z(const T* __restrict__ H, const T* __restr
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (int)((rows + G::BP - 1) / G::BP), TQ = (f + G::BQ / 2 - 1) / (G::BQ / 2);
   int tp, tq;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), TP, TQ, 4, tp, tq);
+  // groups of 8 token tiles sweep every weight tile: the weights (a few
+  // hundred MB at most) stay in the last-level cache while the tokens stream
+  // from HBM once, not once per group of weight tiles
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), TQ, TP, 8, tq, tp);
   const int64_t t0 = (int64_t)tp * G::BP;
   const int j0 = tq * (G::BQ / 2);
   const uint64_t ldb = (uint64_t)d * esz<T>();
@@ -128,29 +131,49 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z(const T* __restrict__ H, const T* __restr
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
   // Each wave's 64 Q rows are 32 W_gate rows (blocks 0, 1) then the same 32
-  // W_up rows (blocks 2, 3): block jj pairs with block jj + 2.
-  static_assert(G::NQB == 4 && G::BM == 16, "two gate/up block pairs per wave");
+  // W_up rows (blocks 2, 3): block jj pairs with block jj + 2.  Z replaces the
+  // gate value in place.
+  static_assert(G::NQB == 4 && G::BM == 16 && G::GPB == 1, "two gate/up block pairs per wave");
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int j = j0 + (wave_id() % G::WQ) * 32 + jj * 16 + (lane_id() & 15);
-    if (j >= f) continue;
+  for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
-    for (int i = 0; i < G::NPB; ++i) {
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int g = 0; g < G::GPB; ++g) {
-        const int64_t row = t0 + G::acc_p(i, g);
-        if (row >= rows) continue;
-        float z[4];
+      for (int e = 0; e < 4; ++e) acc[i][jj][e] = silu_f(acc[i][jj][e]) * acc[i][jj + 2][e];
+  const int jl = (wave_id() % G::WQ) * 32 + (lane_id() & 15);      // local column of block jj = 0
+  const int jn = min(G::BQ / 2, f - j0);
+  const int tn = (int)min<int64_t>(G::BP, rows - t0);
+
+  // Zt [b, j, t]: staged as [128 columns][256 tokens]; a 16-byte piece holds
+  // 8 (bf16) or 4 (fp32) tokens, which never straddle a batch row (n % 8 == 0).
+  {
+    const Staged<T, G::BP> st{smem};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = silu_f(acc[i][jj][4 * g + e]) * acc[i][jj + 2][4 * g + e];
-        const int64_t b = row / n, t = row - b * n;
-        store4(Zt + (b * f + j) * (int64_t)n + t, z[0], z[1], z[2], z[3]);
-        if (Z != nullptr) {
+    for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Z[(row + e) * f + j] = from_f32<T>(z[e]);
-        }
-      }
-    }
+      for (int jj = 0; jj < 2; ++jj)
+        st.put4(jl + 16 * jj, G::acc_p(i, 0), acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
+    __syncthreads();
+    st.template flush<G::NT>(jn, [&](int r, int col) -> T* {
+      if (col >= tn) return nullptr;
+      const int64_t tok = t0 + col, b = tok / n;
+      return Zt + (b * f + j0 + r) * (int64_t)n + (tok - b * n);
+    });
+    __syncthreads();
+  }
+  // Z [t, j]: staged as [256 tokens][128 columns]
+  if (Z != nullptr) {
+    const Staged<T, G::BQ / 2> sz{smem};
+#pragma unroll
+    for (int i = 0; i < G::NPB; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sz.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj][e]);
+    __syncthreads();
+    sz.template flush<G::NT>(tn, [&](int r, int col) -> T* {
+      return col < jn ? Z + (t0 + r) * f + j0 + col : nullptr;
+    });
   }
 }
 
@@ -163,7 +186,10 @@ TTT_GEMM_KERNEL(Wide) void k_produce_vhat(const T* __restrict__ Y, const T* __re
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (int)((rows + G::BP - 1) / G::BP), TQ = (d + G::BQ - 1) / G::BQ;
   int tp, tq;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), TP, TQ, 4, tp, tq);
+  // groups of 8 token tiles sweep every weight tile: the weights (a few
+  // hundred MB at most) stay in the last-level cache while the tokens stream
+  // from HBM once, not once per group of weight tiles
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), TQ, TP, 8, tq, tp);
   const int64_t t0 = (int64_t)tp * G::BP;
   const int o0 = tq * G::BQ;
   const uint64_t ldb = (uint64_t)d * esz<T>();
@@ -176,20 +202,30 @@ TTT_GEMM_KERNEL(Wide) void k_produce_vhat(const T* __restrict__ Y, const T* __re
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
+  // Vt [b, o, t]: staged as [output channel][token] in as many passes as the
+  // stage area needs (one for bf16, two for fp32).
+  const int tn = (int)min<int64_t>(G::BP, rows - t0);
+  constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
+  const Staged<T, G::BP> st{smem};
 #pragma unroll
-  for (int j = 0; j < G::NQB; ++j) {
-    const int o = o0 + G::acc_q(j);
-    if (o >= d) continue;
+  for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
-    for (int i = 0; i < G::NPB; ++i)
+    for (int j = 0; j < G::NQB; ++j) {
+      const int q = G::acc_q(j) - ps * RPP;
+      if (q < 0 || q >= RPP) continue;
 #pragma unroll
-      for (int g = 0; g < G::GPB; ++g) {
-        const int64_t row = t0 + G::acc_p(i, g);
-        if (row >= rows) continue;
-        const int64_t b = row / n, t = row - b * n;
-        store4(Vt + (b * d + o) * (int64_t)n + t, scale * acc[i][j][4 * g], scale * acc[i][j][4 * g + 1],
-               scale * acc[i][j][4 * g + 2], scale * acc[i][j][4 * g + 3]);
-      }
+      for (int i = 0; i < G::NPB; ++i)
+        st.put4(q, G::acc_p(i, 0), scale * acc[i][j][0], scale * acc[i][j][1], scale * acc[i][j][2],
+                scale * acc[i][j][3]);
+    }
+    __syncthreads();
+    st.template flush<G::NT>(RPP, [&](int r, int col) -> T* {
+      const int o = o0 + ps * RPP + r;
+      if (o >= d || col >= tn) return nullptr;
+      const int64_t tok = t0 + col, b = tok / n;
+      return Vt + (b * d + o) * (int64_t)n + (tok - b * n);
+    });
+    __syncthreads();
   }
 }
 
@@ -412,19 +448,24 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Z, const T* __restrict_
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
-  const bool full = i0 + G::BP <= d && t0 + G::BQ <= C_;
+  // O [token, channel]: staged as [token][channel] (one pass for bf16, two for fp32)
+  const int tn = min(G::BQ, C_ - t0), in_ = min(G::BP, d - i0);
+  constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
+  const Staged<T, G::BP> st{smem};
 #pragma unroll
-  for (int j = 0; j < G::NQB; ++j) {
-    const int t = G::acc_q(j);
+  for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
-    for (int i = 0; i < G::NPB; ++i)
+    for (int j = 0; j < G::NQB; ++j) {
+      const int q = G::acc_q(j) - ps * RPP;
+      if (q < 0 || q >= RPP) continue;
 #pragma unroll
-      for (int g = 0; g < G::GPB; ++g) {
-        const int p = i0 + G::acc_p(i, g);
-        if (full || (t0 + t < C_ && p < d))
-          store4(O + (row0 + t) * d + p, acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                 acc[i][j][4 * g + 3]);
-      }
+      for (int i = 0; i < G::NPB; ++i) st.put4(q, G::acc_p(i, 0), acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    }
+    __syncthreads();
+    st.template flush<G::NT>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
+      return col < in_ ? O + (row0 + ps * RPP + r) * d + i0 + col : nullptr;
+    });
+    __syncthreads();
   }
 }
 
