@@ -67,6 +67,10 @@ __device__ __forceinline__ void unpack8(u32x4 w, float* o) {
   }
 }
 
-__device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
+// Logistic function and SiLU from the hardware exponential and reciprocal
+// (v_exp_f32, v_rcp_f32, about 1 ulp each) rather than an IEEE division
+// sequence.  exp(-x) overflowing to +inf for very negative x gives 0.
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
 
 }  // namespace ttt

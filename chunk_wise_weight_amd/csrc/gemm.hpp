@@ -15,11 +15,13 @@
 // resource's range, which the hardware returns as zero: no branches.
 //
 // LDS layout of a tile: rows of 128 B; the 16-byte chunk c of row r sits in
-// slot c ^ (r & 7), so the 16-byte fragment reads of 8 consecutive rows hit 8
-// different bank groups.  The DMA reaches this layout by letting lane L of an
-// instruction fetch chunk (L & 7) ^ (L >> 3) of its row.  Two stages of
-// (BP + BQ) x 128 B: step k+1 is in flight while step k is multiplied; one
-// barrier per step.
+// slot c ^ ((r >> 1) & 7).  The LDS serves a 16-byte read for 16 lanes at a
+// time across 64 four-byte banks (256 B); an MFMA fragment read has those 16
+// lanes on 16 consecutive rows at one chunk, and (r & 1, slot) then takes 16
+// different values, one per 16-byte bank group.  The DMA reaches this layout
+// by letting lane L of an instruction fetch chunk (L & 7) ^ swizzle(row) of
+// its row.  Two stages of (BP + BQ) x 128 B: step k+1 is in flight while step
+// k is multiplied; one barrier per step.
 //
 // MFMA mapping (v_mfma_f32_16x16x32_bf16, or 4 x v_mfma_f32_16x16x4_f32 for
 // fp32): P feeds the instruction's A slot, Q its B slot.  Operand lane l holds
@@ -38,7 +40,8 @@ constexpr unsigned kOOB = 0x80000000u;     // any offset >= this is outside ever
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ int lds_swz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ lds_swz(row)) << 4); }
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
@@ -107,7 +110,8 @@ struct DmaOp {
   static constexpr int NI = ROWS / (8 * NW);
   static_assert(NI >= 1 && NI * 8 * NW == ROWS, "tile rows must split evenly over the waves");
   __amdgpu_buffer_rsrc_t rs0, rs1;
-  unsigned off[NI];
+  unsigned off[NI];    // this lane's row offset, or kOOB for rows outside the matrix
+  unsigned coff;       // byte offset of the chunk this lane fetches within the K step (even 8-row blocks)
   unsigned kbytes;
 
   // rows_valid: rows of each source matrix inside this tile; ld_bytes: row pitch.
@@ -124,18 +128,19 @@ struct DmaOp {
       const int mr = DUAL ? ((r >> 6) << 5) + (r & 31) : r;
       off[i] = mr < rows_valid ? (unsigned)(mr * ld_bytes) : kOOB;
     }
+    // Row r = 8 b + (L >> 3) of 8-row block b has swizzle (r >> 1) & 7 =
+    // 4 (b & 1) + (L >> 4): one base offset, flipped by 64 B in odd blocks.
+    coff = (unsigned)(((L & 7) ^ (L >> 4)) << 4);
   }
   __device__ __forceinline__ void issue(int ks, char* tile) const {
-    const unsigned L = lane_id();
-    const unsigned kb = (unsigned)ks * 128u + (((L & 7u) ^ (L >> 3)) << 4);
-    const bool kin = kb < kbytes;
     const int w = wave_id();
     char* base = tile + w * NI * 1024;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const bool second = DUAL && ((((w * NI + i) * 8) >> 5) & 1);
+      const unsigned kb = (unsigned)ks * 128u + (coff ^ ((unsigned)((w * NI + i) & 1) << 6));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rs1 : rs0, (lds_ptr_t)(base + i * 1024), 16,
-                                               kin ? off[i] + kb : kOOB, 0, 0, 0);
+                                               kb < kbytes ? off[i] + kb : kOOB, 0, 0, 0);
     }
   }
 };
@@ -168,25 +173,37 @@ __device__ __forceinline__ void load_frags(const char* tp, const char* tq, int g
   for (int j = 0; j < C::NQB; ++j) qf[j] = *reinterpret_cast<const u32x4*>(tq + lds_off(qrow + C::BM * j, chunk));
 }
 
-// One K step (two groups of 32 k for bf16 / 16 k for fp32).  Fragments are
-// double-buffered in registers: the LDS reads of group 1 are issued before
-// the MFMAs of group 0, and scheduling fences keep the compiler from sinking
-// them back next to their use.
+// One K step (two groups of 32 k for bf16 / 16 k for fp32).  Only group 0's
+// fragments are read before the first MFMA; group 1's LDS reads are spread
+// over group 0's MFMAs (two MFMAs, then one read), so that the eight waves of
+// a workgroup, which leave the step barrier together, do not all stall on one
+// burst of LDS reads.  Scheduling fences keep the compiler to that order.
 template <typename T, class C, class Acc>
 __device__ __forceinline__ void compute_stage(const char* tp, const char* tq, Acc& acc) {
+  constexpr int NR = C::NPB + C::NQB;              // fragment reads per group
+  constexpr int NM = C::NPB * C::NQB;              // MFMAs per group (x4 for fp32)
+  constexpr int MPM = sizeof(T) == 2 ? 1 : 4;      // MFMA instructions per block and group
+  static_assert(2 * NR <= NM * MPM, "enough MFMAs to cover the next group's reads");
   u32x4 pf[2][C::NPB], qf[2][C::NQB];
   load_frags<C>(tp, tq, 0, pf[0], qf[0]);
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<C>(tp, tq, 1, pf[1], qf[1]);
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    const int cur = g & 1;
-    if (g < 1) load_frags<C>(tp, tq, g + 1, pf[cur ^ 1], qf[cur ^ 1]);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < C::NPB; ++i)
 #pragma unroll
-    for (int i = 0; i < C::NPB; ++i)
+    for (int j = 0; j < C::NQB; ++j) mma(acc[i][j], pf[0][i], qf[0][j], (T*)nullptr);
 #pragma unroll
-      for (int j = 0; j < C::NQB; ++j) mma(acc[i][j], pf[cur][i], qf[cur][j], (T*)nullptr);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int r = 0; r < NR; ++r) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // 2 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // 1 LDS read
   }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM * MPM - 2 * NR, 0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < C::NPB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NQB; ++j) mma(acc[i][j], pf[1][i], qf[1][j], (T*)nullptr);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 struct NoHook {

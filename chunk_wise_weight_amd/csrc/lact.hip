@@ -238,7 +238,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_dh(const T* __restrict__ R, const T* __restric
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float dh_ = acc[ib][jq][4 * g + e];
-          const float s = 1.0f / (1.0f + __expf(-a[e]));
+          const float s = sigmoid_f(a[e]);
           du[e] = dh_ * a[e] * s;
           da[e] = dh_ * u[e] * s * (1.0f + a[e] * (1.0f - s));
         }
