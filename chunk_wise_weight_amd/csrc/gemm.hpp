@@ -95,9 +95,23 @@ __device__ __forceinline__ void grouped_tile(int id, int TP, int TQ, int G, int&
 
 // ---------------------------------------------------------------- LDS DMA operands
 
+// Buffer resource over [base, base + bytes).  Every base and extent used here
+// is the same for the whole workgroup; reading the words through
+// readfirstlane tells the compiler so, which keeps the resource in scalar
+// registers (a value it cannot prove uniform -- e.g. one computed by a
+// vector-ALU integer division -- would otherwise be wrapped in a per-lane
+// loop around every load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes) {
   const unsigned n = bytes >= (uint64_t)kOOB ? kOOB - 1u : (unsigned)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, 0x00020000);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  // readfirstlane works on int: each half goes back through unsigned before it
+  // is widened, so that bit 31 of the low half is not sign-extended into the
+  // high half.
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+  const uint64_t ub = ((uint64_t)hi << 32) | (uint64_t)lo;
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ub), (short)0,
+                                           __builtin_amdgcn_readfirstlane((int)n), 0x00020000);
 }
 
 // K-contiguous operand moved by DMA into a ROWS-row tile by NW waves: DMA
@@ -109,7 +123,10 @@ template <int NW, int ROWS, bool DUAL = false>
 struct DmaOp {
   static constexpr int NI = ROWS / (8 * NW);
   static_assert(NI >= 1 && NI * 8 * NW == ROWS, "tile rows must split evenly over the waves");
-  __amdgpu_buffer_rsrc_t rs0, rs1;
+  // DUAL: each wave's 8 NI rows must lie in one 32-row block, so that the
+  // wave reads one matrix and holds a single resource
+  static_assert(!DUAL || 32 % (8 * NI) == 0, "dual: each wave reads rows of one 32-row block");
+  __amdgpu_buffer_rsrc_t rs;
   unsigned off[NI];    // this lane's row offset, or kOOB for rows outside the matrix
   unsigned coff;       // byte offset of the chunk this lane fetches within the K step (even 8-row blocks)
   unsigned kbytes;
@@ -120,8 +137,9 @@ struct DmaOp {
     kbytes = kbytes_;
     const int w = wave_id(), L = lane_id();
     const uint64_t span = rows_valid > 0 ? (uint64_t)(rows_valid - 1) * ld_bytes + kbytes_ : 0;
-    rs0 = make_rsrc(base0, span);
-    rs1 = make_rsrc(DUAL ? base1 : base0, span);
+    // block of this wave's first row: even blocks come from base0, odd from base1
+    const bool second = DUAL && ((((w * NI) * 8) >> 5) & 1);
+    rs = make_rsrc(second ? base1 : base0, span);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int r = (w * NI + i) * 8 + (L >> 3);
@@ -137,9 +155,8 @@ struct DmaOp {
     char* base = tile + w * NI * 1024;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const bool second = DUAL && ((((w * NI + i) * 8) >> 5) & 1);
       const unsigned kb = (unsigned)ks * 128u + (coff ^ ((unsigned)((w * NI + i) & 1) << 6));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(second ? rs1 : rs0, (lds_ptr_t)(base + i * 1024), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(base + i * 1024), 16,
                                                kb < kbytes ? off[i] + kb : kOOB, 0, 0, 0);
     }
   }
