@@ -301,6 +301,27 @@ struct Staged {
       if (p != nullptr) *reinterpret_cast<u32x4*>(p) = *reinterpret_cast<const u32x4*>(base + r * RB + ((c ^ (r & 15)) << 4));
     }
   }
+  // Transposed copy-out: output row c (c < ncols) is column c of the staged
+  // rows [0, nrows) (nrows a multiple of EPP); each 16-byte output piece
+  // gathers EPP consecutive staged rows.  A wave covers 8 output rows x 8
+  // pieces, so its stores form 128-byte runs.  dst(c, r) is the address of
+  // output element r of row c, or nullptr to skip.
+  template <int NT, class Dst>
+  __device__ __forceinline__ void flush_t(int ncols, int nrows, Dst&& dst) const {
+    const int ppc = nrows / EPP;                               // pieces per output row
+    const int groups = (ncols + 7) / 8, chunks = (ppc + 7) / 8;
+    for (int idx = threadIdx.x; idx < groups * chunks * 64; idx += NT) {
+      const int lane = idx & 63, blk = idx >> 6;
+      const int c = (blk / chunks) * 8 + (lane & 7), pc = (blk % chunks) * 8 + (lane >> 3);
+      if (c >= ncols || pc >= ppc) continue;
+      TO* p = dst(c, pc * EPP);
+      if (p == nullptr) continue;
+      TO v[EPP];
+#pragma unroll
+      for (int e = 0; e < EPP; ++e) v[e] = *reinterpret_cast<const TO*>(base + off(pc * EPP + e, c));
+      *reinterpret_cast<u32x4*>(p) = *reinterpret_cast<const u32x4*>(v);
+    }
+  }
 };
 
 }  // namespace ttt

@@ -498,24 +498,67 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Z, const T* __restr
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
+  static_assert(G::GPB == 1, "one accumulator group per block");
+  const int tn = min(G::BP, C_ - t0), in_ = min(G::BQ, d - i0);
+  constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem;
+
+  // O [token, channel]: staged as [token][channel], in passes over token rows
+  {
+    constexpr int RPP = G::BP / PASSES;
+    const Staged<T, G::BQ> st{smem};
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+#pragma unroll
+      for (int ib = 0; ib < G::NPB; ++ib) {
+        const int p = G::acc_p(ib, 0) - ps * RPP;
+        if (p < 0 || p >= RPP) continue;
+#pragma unroll
+        for (int j = 0; j < G::NQB; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.put1(p + e, G::acc_q(j), acc[ib][j][e]);
+      }
+      __syncthreads();
+      st.template flush<G::NT>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
+        return col < in_ ? O + (row0 + t0 + ps * RPP + r) * d + i0 + col : nullptr;
+      });
+      __syncthreads();
+    }
+  }
+  // residual in place: R = O - V^ (fp32), then Rt [b, channel, token] staged as
+  // [channel][token] in passes over channel rows
+  // (branch-free: a lane outside the matrix reads the nearest valid element,
+  // whose result is never stored)
 #pragma unroll
   for (int j = 0; j < G::NQB; ++j) {
-    const int i = i0 + G::acc_q(j);
-    if (i >= d) continue;
+    const int i = min(i0 + G::acc_q(j), d - 1);
 #pragma unroll
-    for (int ib = 0; ib < G::NPB; ++ib)
+    for (int ib = 0; ib < G::NPB; ++ib) {
+      const int t = min(t0 + G::acc_p(ib, 0), C_ - 4);
+      const f32x4 v = load4(Vt + ((int64_t)b * d + i) * n + (int64_t)c * C_ + t);
 #pragma unroll
-      for (int g = 0; g < G::GPB; ++g) {
-        const int t = t0 + G::acc_p(ib, g);
-        if (t >= C_) continue;
-        float a[4];
+      for (int e = 0; e < 4; ++e) acc[ib][j][e] -= v[e];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  {
+    constexpr int RPP = G::BQ / PASSES;
+    const Staged<T, G::BP> st{smem};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) a[e] = acc[ib][j][4 * g + e];
+    for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) O[(row0 + t + e) * d + i] = from_f32<T>(a[e]);
-        const f32x4 v = load4(Vt + ((int64_t)b * d + i) * n + (int64_t)c * C_ + t);
-        store4(Rt + ((int64_t)b * d + i) * C_ + t, a[0] - v[0], a[1] - v[1], a[2] - v[2], a[3] - v[3]);
+      for (int j = 0; j < G::NQB; ++j) {
+        const int q = G::acc_q(j) - ps * RPP;
+        if (q < 0 || q >= RPP) continue;
+#pragma unroll
+        for (int ib = 0; ib < G::NPB; ++ib)
+          st.put4(q, G::acc_p(ib, 0), acc[ib][j][0], acc[ib][j][1], acc[ib][j][2], acc[ib][j][3]);
       }
+      __syncthreads();
+      st.template flush<G::NT>(max(0, min(RPP, in_ - ps * RPP)), [&](int r, int col) -> T* {
+        return col < tn ? Rt + ((int64_t)b * d + i0 + ps * RPP + r) * C_ + t0 + col : nullptr;
+      });
+      __syncthreads();
+    }
   }
 }
 

@@ -103,36 +103,52 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restr
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
   // Each wave's 64 Q rows are 32 W1 rows (blocks 0, 1) then the same 32 W3 rows
-  // (blocks 2, 3): block jj pairs with block jj + 2.
-  static_assert(G::NQB == 4 && G::BM == 16, "two W1/W3 block pairs per wave");
-  T* hh = Hh + ((int64_t)part * BH + bh) * C * m;
+  // (blocks 2, 3): block jj pairs with block jj + 2.  The outputs go through
+  // the stage area one at a time: A^T and U^T (keys), then Hh = silu(A) * U is
+  // formed in place of A, then Hh^T (keys) and Hh.
+  static_assert(G::NQB == 4 && G::BM == 16 && G::GPB == 1, "two W1/W3 block pairs per wave");
+  const int jl = (wave_id() % G::WQ) * 32 + (lane_id() & 15);      // local column of block jj = 0
+  const int jn = min(G::BQ / 2, m - j0), tn = min(G::BP, nrows - r0);
+  // [column][token] tile of the key rows: rows j, tokens contiguous
+  auto stage_t = [&](T* dstbase, int half) {
+    const Staged<T, G::BP> st{smem};
 #pragma unroll
-  for (int jj = 0; jj < 2; ++jj) {
-    const int j = j0 + (wave_id() % G::WQ) * 32 + jj * 16 + (lane_id() & 15);
-    if (j >= m) continue;
-    const int64_t tb = ((int64_t)bh * m + j) * C;     // row j of the [BH, m, C] buffers
+    for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
-    for (int i = 0; i < G::NPB; ++i) {
+      for (int jj = 0; jj < 2; ++jj)
+        st.put4(jl + 16 * jj, G::acc_p(i, 0), acc[i][jj + half][0], acc[i][jj + half][1], acc[i][jj + half][2],
+                acc[i][jj + half][3]);
+    __syncthreads();
+    st.template flush<G::NT>(jn, [&](int r, int col) -> T* {
+      return col < tn ? dstbase + ((int64_t)bh * m + j0 + r) * C + r0 + col : nullptr;
+    });
+    __syncthreads();
+  };
+  if (part) {
+    stage_t(At, 0);
+    stage_t(Ut, 2);
+  }
 #pragma unroll
-      for (int g = 0; g < G::GPB; ++g) {
-        const int r = r0 + G::acc_p(i, g);
-        if (r >= nrows) continue;
-        float a[4], u[4], h[4];
+  for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = acc[i][jj][4 * g + e];
-          u[e] = acc[i][jj + 2][4 * g + e];
-          h[e] = silu_f(a[e]) * u[e];
-        }
+    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hh[(int64_t)(r + e) * m + j] = from_f32<T>(h[e]);
-        if (part) {
-          store4(HhT + tb + r, h[0], h[1], h[2], h[3]);
-          store4(At + tb + r, a[0], a[1], a[2], a[3]);
-          store4(Ut + tb + r, u[0], u[1], u[2], u[3]);
-        }
-      }
-    }
+      for (int e = 0; e < 4; ++e) acc[i][jj][e] = silu_f(acc[i][jj][e]) * acc[i][jj + 2][e];
+  if (part) stage_t(HhT, 0);
+  // Hh [part, bh, token, column]: staged as [token][column]
+  {
+    const Staged<T, G::BQ / 2> sz{smem};
+#pragma unroll
+    for (int i = 0; i < G::NPB; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sz.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj][e]);
+    __syncthreads();
+    T* hh = Hh + ((int64_t)part * BH + bh) * C * m;
+    sz.template flush<G::NT>(tn, [&](int r, int col) -> T* {
+      return col < jn ? hh + (int64_t)(r0 + r) * m + j0 + col : nullptr;
+    });
   }
 }
 
@@ -168,30 +184,42 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __rest
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
+  static_assert(G::GPB == 1, "one accumulator group per block");
+  const int tn = min(G::BQ, nrows - r0), in_ = min(G::BP, dh - i0);
+  constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
+  // O (queries) or R = Y - V (keys, formed in fp32 block by block), [token][channel]:
+  // staged by token rows; for keys R^T [bh, channel, token] is copied out of the
+  // same staged (rounded) tile, transposed.
+  const Staged<T, G::BP> st{smem};
+  T* base = part ? R + (int64_t)bh * C * dh : O + ((int64_t)bh * n + (int64_t)sr.qc * C) * dh;
 #pragma unroll
-  for (int jq = 0; jq < G::NQB; ++jq) {
-    const int r = r0 + G::acc_q(jq);
-    if (r >= nrows) continue;
+  for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
-    for (int ib = 0; ib < G::NPB; ++ib)
+    for (int jq = 0; jq < G::NQB; ++jq) {
+      const int q = G::acc_q(jq) - ps * RPP;
+      if (q < 0 || q >= RPP) continue;
+      // a lane outside the matrix reads the nearest valid element of V (never stored)
+      const int r = min(r0 + G::acc_q(jq), nrows - 1);
 #pragma unroll
-      for (int g = 0; g < G::GPB; ++g) {
-        const int i = i0 + G::acc_p(ib, g);
-        if (i >= dh) continue;
-        float y[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = acc[ib][jq][4 * g + e];
-        if (!part) {
-          store4(O + ((int64_t)bh * n + (int64_t)sr.qc * C + r) * dh + i, y[0], y[1], y[2], y[3]);
-        } else {
-          const f32x4 vv = load4(v + ((int64_t)bh * n + (int64_t)sr.kc * C + r) * dh + i);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] -= vv[e];
-          store4(R + ((int64_t)bh * C + r) * dh + i, y[0], y[1], y[2], y[3]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Rt[((int64_t)bh * dh + i + e) * C + r] = from_f32<T>(y[e]);
+      for (int ib = 0; ib < G::NPB; ++ib) {
+        f32x4 y = acc[ib][jq];
+        if (part) {
+          const int i = min(i0 + G::acc_p(ib, 0), dh - 4);
+          y -= load4(v + ((int64_t)bh * n + (int64_t)sr.kc * C + r) * dh + i);
         }
+        st.put4(q, G::acc_p(ib, 0), y[0], y[1], y[2], y[3]);
       }
+    }
+    __syncthreads();
+    const int rows = max(0, min(RPP, tn - ps * RPP));
+    st.template flush<G::NT>(rows, [&](int rr, int col) -> T* {
+      return col < in_ ? base + (int64_t)(r0 + ps * RPP + rr) * dh + i0 + col : nullptr;
+    });
+    if (part)
+      st.template flush_t<G::NT>(in_, rows, [&](int ci, int rr) -> T* {
+        return Rt + ((int64_t)bh * dh + i0 + ci) * C + r0 + ps * RPP + rr;
+      });
+    __syncthreads();
   }
 }
 
