@@ -86,7 +86,7 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
       off += align_up((size_t)p->B * p->k * DF * 4);
     } else if (p->S > 1) {
       p->off_Wp = off;
-      off += align_up((size_t)p->B * (p->k - p->k / p->S) * DF * 4);
+      off += align_up((size_t)p->B * (p->k - p->k / p->S) * DF * p->esz);
       p->off_Tot = off;
       off += align_up((size_t)p->B * (p->S - 1) * DF * 4);
     }
@@ -144,7 +144,7 @@ int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Ztv
   T* Wc = (T*)(ws + p.off_Wc);
   int st;
   if (p.fused) {
-    st = dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (float*)(ws + p.off_Wp), (float*)(ws + p.off_Tot),
+    st = dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (T*)(ws + p.off_Wp), (float*)(ws + p.off_Tot),
                                               B, n, d, f, C, p.S, s));   // Vt carries eta
   } else {
     float* dW = (float*)(ws + p.off_dW);
@@ -366,12 +366,13 @@ int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const v
                                            eta, s));
 }
 
-static size_t update_scan_ws(const ttt_inplace_shape* s) {
+static size_t update_scan_ws(const ttt_inplace_shape* s, int dtype) {
   const int64_t k = s->seq_len / s->chunk;
   const int S = ttt::update_scan_segments(s->d_model, s->d_ff, k);
   if (S == 1) return 0;
   const size_t DF = (size_t)s->d_model * s->d_ff;
-  return align_up((size_t)s->batch * (k - k / S) * DF * 4) + align_up((size_t)s->batch * (S - 1) * DF * 4);
+  const size_t esz = dtype == TTT_BF16 ? 2 : 4;
+  return align_up((size_t)s->batch * (k - k / S) * DF * esz) + align_up((size_t)s->batch * (S - 1) * DF * 4);
 }
 
 int ttt_update_scan_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes) {
@@ -379,7 +380,7 @@ int ttt_update_scan_workspace_bytes(const ttt_inplace_shape* shape, int dtype, s
   int st = check_inplace_shape(shape, dtype);
   if (st != TTT_OK) return st;
   if (shape->chunk % kstep(dtype) != 0) return TTT_ERR_UNSUPPORTED;
-  *bytes = update_scan_ws(shape);
+  *bytes = update_scan_ws(shape, dtype);
   return TTT_OK;
 }
 
@@ -401,17 +402,18 @@ int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void*
     return dev(ttt::launch_chunk_scan<float>(nullptr, (const float*)W_down0, nullptr, W_final, B, 0, df, 0.f, s));
   }
   if (!ok_ptr(Zt) || !ok_ptr(Vt) || !ok_ptr(Wc)) return TTT_ERR_ARG;
-  const size_t need = update_scan_ws(shape);
+  const size_t need = update_scan_ws(shape, dtype);
   if (workspace_bytes < need || (need > 0 && !ok_ptr(workspace))) return TTT_ERR_WORKSPACE;
   const int k = n / C, S = ttt::update_scan_segments(d, f, k);
   char* ws = (char*)workspace;
-  float* Wp = S > 1 ? (float*)ws : nullptr;
-  float* Tot = S > 1 ? (float*)(ws + align_up((size_t)B * (k - k / S) * df * 4)) : nullptr;
+  const size_t esz = dtype == TTT_BF16 ? 2 : 4;
+  void* Wp = S > 1 ? (void*)ws : nullptr;
+  float* Tot = S > 1 ? (float*)(ws + align_up((size_t)B * (k - k / S) * df * esz)) : nullptr;
   if (dtype == TTT_BF16)
     return dev(ttt::launch_chunk_update_scan<bf16>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)W_down0, (bf16*)Wc,
-                                                   W_final, Wp, Tot, B, n, d, f, C, S, s));
+                                                   W_final, (bf16*)Wp, Tot, B, n, d, f, C, S, s));
   return dev(ttt::launch_chunk_update_scan<float>((const float*)Zt, (const float*)Vt, (const float*)W_down0,
-                                                  (float*)Wc, W_final, Wp, Tot, B, n, d, f, C, S, s));
+                                                  (float*)Wc, W_final, (float*)Wp, Tot, B, n, d, f, C, S, s));
 }
 
 int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Wc, void* O, void* stream) {

@@ -324,14 +324,14 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW
 // To fill the chip when the state has few tiles, the sequence is cut into S
 // segments of k / S chunks that run side by side.  Segment 0 starts from
 // W_down0 and writes the states W_c of its chunks in the operand dtype; a
-// later segment starts from zero and writes fp32 partial states to Wp
+// later segment starts from zero and writes partial states to Wp (operand dtype)
 // (chunks after its first) and its total to Tot[b, s - 1] -- except the last
 // segment, whose total goes to W_final.  k_scan_fixup then adds the earlier
 // segments' totals.  With S = 1 the kernel alone produces every output.
 template <typename T>
 struct SnapshotHook {
   T* Wc;              // [k, d, f] states of this batch row (segment 0)
-  float* Wp;          // partial states of this batch row; chunk c at Wp + (c - kS) d f (later segments)
+  T* Wp;              // partial states of this batch row; chunk c at Wp + (c - kS) d f (later segments)
   int steps_per_chunk, c0, c1, kS, j0, i0, d, f;
   template <class A>
   __device__ __forceinline__ void operator()(int ks, A& acc) const {
@@ -349,7 +349,7 @@ struct SnapshotHook {
 
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T* __restrict__ Vt,
-                                               const T* __restrict__ W0, T* __restrict__ Wc, float* __restrict__ Wp,
+                                               const T* __restrict__ W0, T* __restrict__ Wc, T* __restrict__ Wp,
                                                float* __restrict__ Tot, float* __restrict__ Wf, int n, int d, int f,
                                                int C_, int S) {
   using G = Wide;
@@ -394,14 +394,14 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
 // 1..S-1, and to W_final, the total of the segments before it, rounding each
 // state once to the operand dtype.  Four elements per thread, grid.y = batch.
 template <typename T>
-__global__ __launch_bounds__(256) void k_scan_fixup(T* __restrict__ Wc, const float* __restrict__ Wp,
+__global__ __launch_bounds__(256) void k_scan_fixup(T* __restrict__ Wc, const T* __restrict__ Wp,
                                                     const float* __restrict__ Tot, float* __restrict__ Wf, int k,
                                                     int S, int64_t df) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= df) return;
   const int b = blockIdx.y, kS = k / S;
   T* wc = Wc + (int64_t)b * k * df + e;
-  const float* wp = Wp + (int64_t)b * (k - kS) * df + e;
+  const T* wp = Wp + (int64_t)b * (k - kS) * df + e;
   const float* tot = Tot + (int64_t)b * (S - 1) * df + e;
   f32x4 off = load4(tot);                                   // W_down0 + segment 0
   for (int sg = 1; sg < S; ++sg) {
@@ -663,7 +663,7 @@ hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int
 }
 
 template <typename T>
-hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, float* Wp, float* Tot,
+hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
                                     int B, int n, int d, int f, int Cs, int S, hipStream_t s) {
   const int64_t tiles = cdiv(f, kWB) * cdiv(d, kWB) * B * S;
   if (tiles == 0) return hipSuccess;
@@ -708,7 +708,7 @@ hipError_t launch_mse_chunk(const T* Z, const T* Zt, const T* Vt, const T* W0, c
   template hipError_t launch_chunk_delta<T>(const T*, const T*, float*, int, int, int, int, int, hipStream_t);   \
   template hipError_t launch_chunk_scan<T>(const float*, const T*, T*, float*, int, int, int64_t, float,         \
                                            hipStream_t);                                                          \
-  template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, float*, float*, int,  \
+  template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, T*, float*, int,      \
                                                   int, int, int, int, int, hipStream_t);                          \
   template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int,          \
                                       hipStream_t);                                                               \

@@ -24,7 +24,7 @@ template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
                              hipStream_t s);
 template <typename T>
-hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, float* Wp, float* Tot,
+hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
                                     int B, int n, int d, int f, int C, int S, hipStream_t s);
 
 // Number of sequence segments the fused update-scan runs side by side: more

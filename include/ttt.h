@@ -163,7 +163,8 @@ int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const v
                    const float* dW, void* Wc, float* W_final, void* stream);
 
 /* Scratch of ttt_chunk_update_scan for these sizes: 0 when the sequence runs
- * as one segment, else the fp32 partial states and segment totals below. */
+ * as one segment, else the partial states (dtype) and segment totals (fp32)
+ * below. */
 int ttt_update_scan_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes);
 
 /* Deltas and scan fused (chunk % 64 == 0 for bf16, % 32 for fp32, else
@@ -175,7 +176,8 @@ int ttt_update_scan_workspace_bytes(const ttt_inplace_shape* shape, int dtype, s
  * chunks 0..c-1; at each chunk boundary the tile writes Wc[b, c], after the
  * last chunk W_final.  When the state has too few tiles to fill the GPU, the
  * sequence runs as S side-by-side segments and a short elementwise pass adds
- * the earlier segments' totals (fp32) before the single rounding to dtype;
+ * the earlier segments' totals (fp32) to the later segments' partial states
+ * (kept in dtype; with bf16 a state of a later segment is thus rounded twice);
  * `workspace` (device, at least ttt_update_scan_workspace_bytes) holds the
  * partial states and may be NULL when that query returns 0.
  * Same outputs as ttt_chunk_delta (on the unscaled target) followed by

@@ -78,7 +78,7 @@ def test_update_scan_segments_and_workspace():
     """The fused update-scan runs the sequence as S segments when that fills the 256 compute units
     markedly better for one batch row (S depends on the state's shape only, so rows do not depend on
     the batch they are in); its scratch holds the fp32 partial states of chunks past the first
-    segment and the S - 1 segment totals."""
+    segment (bf16 here) and the S - 1 fp32 segment totals."""
     al = lambda x: (x + 255) // 256 * 256
 
     def expect(B, n, d, f, C):
@@ -89,7 +89,7 @@ def test_update_scan_segments_and_workspace():
         for cand in (2, 4):
             if k % cand == 0 and fill(tiles * cand) > fill(tiles * S) + 0.05:
                 S = cand
-        return S, (0 if S == 1 else al(B * (k - k // S) * d * f * 4) + al(B * (S - 1) * d * f * 4))
+        return S, (0 if S == 1 else al(B * (k - k // S) * d * f * 2) + al(B * (S - 1) * d * f * 4))
 
     cases = [(1, 131072, 2560, 9728, 4096, 2), (1, 32768, 2560, 9728, 1024, 2), (1, 2048, 1024, 4096, 256, 4),
              (2, 1024, 1024, 4096, 128, 4), (1, 2048, 256, 512, 256, 1), (4, 65536, 2048, 8192, 2048, 1),

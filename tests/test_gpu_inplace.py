@@ -140,7 +140,8 @@ def test_segmented_update_scan(dtype, B, n, d, f, C, segments):
     k = n // C
     DF = d * f
     al = lambda x: (x + 255) // 256 * 256
-    want_ws = al(B * (k - k // segments) * DF * 4) + al(B * (segments - 1) * DF * 4)
+    esz = 2 if dtype == "bf16" else 4
+    want_ws = al(B * (k - k // segments) * DF * esz) + al(B * (segments - 1) * DF * 4)
     assert cw.ttt_update_scan_workspace_bytes(shape, torch.bfloat16 if dtype == "bf16" else torch.float32) == want_ws
     eta = 0.02
     Z, V, W0 = _zv(dtype, B, n, d, f, 31)
