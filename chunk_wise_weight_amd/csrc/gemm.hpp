@@ -225,7 +225,7 @@ __device__ __forceinline__ void compute_stage(const char* tp, const char* tq, Ac
 
 struct NoHook {
   template <class A>
-  __device__ __forceinline__ void operator()(int, A&) const {}
+  __device__ __forceinline__ void operator()(int, A&, char*) const {}
 };
 
 template <class C, class Acc>
@@ -236,8 +236,11 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
     for (int j = 0; j < C::NQB; ++j) acc[i][j] = typename C::Frag{};
 }
 
-// nks steps over K.  hook(ks, acc) runs after step ks, past the barrier; it
-// may read and write global memory but not LDS.
+// nks steps over K.  hook(ks, acc, free_stage) runs after step ks, past the
+// barrier, in every wave.  It may use the stage step ks was read from
+// (C::Stage bytes at free_stage) -- the next write to it is the DMA issued at
+// the start of step ks + 2 -- provided it ends with a barrier; other LDS is
+// off limits.
 template <typename T, class C, class OP, class OQ, class Hook, class Acc>
 __device__ __forceinline__ void mainloop(const OP& op, const OQ& oq, int nks, Acc& acc, char* smem,
                                          const Hook& hook) {
@@ -259,7 +262,7 @@ __device__ __forceinline__ void mainloop(const OP& op, const OQ& oq, int nks, Ac
     compute_stage<T, C>(cur, cur + C::PBytes, acc);
     wait_dma();
     __syncthreads();
-    hook(ks, acc);
+    hook(ks, acc, cur);
   }
 #endif
 }

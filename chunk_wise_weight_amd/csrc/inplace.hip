@@ -263,6 +263,36 @@ __device__ __forceinline__ void store_state(const Acc& acc, TO* __restrict__ out
   });
 }
 
+// store_state through LDS: the [d_model x d_ff] state tile (rows i = Q, columns
+// j = P) is staged in BUFB bytes at buf, in as many passes over its rows as
+// needed, and written out as whole 16-byte pieces along rows.  Every wave must
+// call it; it ends with a barrier.
+template <class G, int BUFB, typename TO, class Acc>
+__device__ __forceinline__ void stage_state(const Acc& acc, TO* __restrict__ out, char* buf, int j0, int i0, int d,
+                                            int f) {
+  static_assert(G::GPB == 1, "one accumulator group per block");
+  constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(TO) + BUFB - 1) / BUFB, RPP = G::BQ / PASSES;
+  static_assert(RPP * PASSES == G::BQ && RPP * G::BP * (int)sizeof(TO) <= BUFB, "passes must tile the rows");
+  const Staged<TO, G::BP> st{buf};
+  const int jn = min(G::BP, f - j0), in_ = min(G::BQ, d - i0);
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+#pragma unroll
+    for (int jb = 0; jb < G::NQB; ++jb) {
+      const int q = G::acc_q(jb) - ps * RPP;
+      if (q < 0 || q >= RPP) continue;
+#pragma unroll
+      for (int ib = 0; ib < G::NPB; ++ib)
+        st.put4(q, G::acc_p(ib, 0), acc[ib][jb][0], acc[ib][jb][1], acc[ib][jb][2], acc[ib][jb][3]);
+    }
+    __syncthreads();
+    st.template flush<G::NT>(max(0, min(RPP, in_ - ps * RPP)), [&](int r, int col) -> TO* {
+      return col < jn ? out + (int64_t)(i0 + ps * RPP + r) * f + j0 + col : nullptr;
+    });
+    __syncthreads();
+  }
+}
+
 // Per-chunk delta dW[b, c] = V^_c^T Z_c (Method §3, step 1), fp32 [B, k, d, f].
 // P = d_ff rows of Zt, Q = d_model rows of Vt, K = the chunk's C tokens.
 template <typename T>
@@ -334,16 +364,14 @@ struct SnapshotHook {
   T* Wp;              // partial states of this batch row; chunk c at Wp + (c - kS) d f (later segments)
   int steps_per_chunk, c0, c1, kS, j0, i0, d, f;
   template <class A>
-  __device__ __forceinline__ void operator()(int ks, A& acc) const {
+  __device__ __forceinline__ void operator()(int ks, A& acc, char* free_stage) const {
     const int done = ks + 1;
     if (done % steps_per_chunk != 0) return;
     const int c = c0 + done / steps_per_chunk;
     if (c >= c1) return;
     const int64_t df = (int64_t)d * f;
-    if (c0 == 0)
-      store_state<Wide>(acc, Wc + (int64_t)c * df, j0, i0, d, f);
-    else
-      store_state<Wide>(acc, Wp + (int64_t)(c - kS) * df, j0, i0, d, f);
+    T* dst = c0 == 0 ? Wc + (int64_t)c * df : Wp + (int64_t)(c - kS) * df;
+    stage_state<Wide, Wide::Stage>(acc, dst, free_stage, j0, i0, d, f);
   }
 };
 
@@ -381,13 +409,13 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
     });
-    store_state<G>(acc, wc, j0, i0, d, f);                                // chunk 0: W_down0
+    stage_state<G, G::Smem>(acc, wc, smem, j0, i0, d, f);                // chunk 0: W_down0
   }
   const SnapshotHook<T> hook{wc, Wp + (int64_t)b * (k - kS) * df, C_ * esz<T>() / 128, c0, c0 + kS, kS,
                              j0, i0, d, f};
   mainloop<T, G>(op, oq, (int)(kbytes / 128), acc, smem, hook);
   float* out = sg == S - 1 ? Wf + (int64_t)b * df : Tot + ((int64_t)b * (S - 1) + sg) * df;
-  store_state<G>(acc, out, j0, i0, d, f);
+  stage_state<G, G::Smem>(acc, out, smem, j0, i0, d, f);
 }
 
 // Completes a segmented update-scan: adds to every partial state of segments
