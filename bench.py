@@ -59,7 +59,7 @@ def kernel_bytes(cfg, esz=2):
     """Algorithmic HBM bytes of each launch: each operand read once, each result written once."""
     T, d, f, k, B = cfg.tokens, cfg.d_model, cfg.d_ff, cfg.n_chunks, cfg.batch
     return {
-        "produce_z": esz * (T * d + 2 * f * d + 2 * T * f),
+        "produce_z": esz * (T * d + 2 * f * d + T * f),
         "produce_vhat": esz * (T * d + d * d + d * cfg.conv_k + T * d),
         "update_scan": esz * (T * f + T * d + d * f + B * k * d * f) + 4 * B * d * f,
         "apply": esz * (T * f + B * k * d * f + T * d),
@@ -99,7 +99,6 @@ def bench_inplace_dot(cfg, steps, warmup):
     B, n, d, f, C = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.chunk
     k = n // C
     dt = g["H"].dtype
-    Z = torch.empty(B, n, f, dtype=dt, device="cuda")
     Zt = torch.empty(B, f, n, dtype=dt, device="cuda")
     Vt = torch.empty(B, d, n, dtype=dt, device="cuda")
     Wc = torch.empty(B, k, d, f, dtype=dt, device="cuda")
@@ -112,13 +111,13 @@ def bench_inplace_dot(cfg, steps, warmup):
 
     def step(ev=None):
         if ev: ev[0].record()
-        cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"], Z, Zt)
+        cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"], None, Zt, with_z=False)
         if ev: ev[1].record()
         cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"], Vt, vws, scale=cfg.eta)
         if ev: ev[2].record()
         cw.ttt_chunk_update_scan(Zt, Vt, g["W_down0"], C, Wc, Wf, uws)
         if ev: ev[3].record()
-        cw.ttt_chunk_apply(Z, Wc, C, O)
+        cw.ttt_chunk_apply(Zt, Wc, C, O)
         if ev: ev[4].record()
 
     for _ in range(warmup):
@@ -132,7 +131,7 @@ def bench_inplace_dot(cfg, steps, warmup):
     wall = time.perf_counter() - t0
     per = {nm: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(steps)) / steps
            for j, nm in enumerate(names)}
-    del Z, Zt, Vt, Wc, O, g
+    del Zt, Vt, Wc, O, g
     return wall, per, Wf
 
 

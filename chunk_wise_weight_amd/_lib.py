@@ -300,19 +300,19 @@ def ttt_chunk_update_scan(Zt, Vt, W_down0, chunk: int, Wc=None, W_final=None, wo
     return Wc, W_final
 
 
-def ttt_chunk_apply(Z, Wc, chunk: int, O=None):
-    """O [B, n, d], O_c = Z_c Wc[b, c]^T."""
-    B, n, f = Z.shape
+def ttt_chunk_apply(Zt, Wc, chunk: int, O=None):
+    """O [B, n, d], O_c = Z_c Wc[b, c]^T, with Z given as its token-contiguous copy Zt [B, f, n]."""
+    B, f, n = Zt.shape
     k, d = Wc.shape[1], Wc.shape[2]
-    dt, dev = Z.dtype, Z.device
-    _need(Z, "Z", (B, n, f), dt, dev)
+    dt, dev = Zt.dtype, Zt.device
+    _need(Zt, "Zt", (B, f, n), dt, dev)
     _need(Wc, "Wc", (B, k, d, f), dt, dev)
     if k * chunk != n:
         raise ValueError("Wc must hold one state per chunk")
     O = torch.empty(B, n, d, dtype=dt, device=dev) if O is None else O
     _need(O, "O", (B, n, d), dt, dev)
     shape = _inplace_shape(B, n, d, f, chunk, 1)
-    _check(lib().ttt_chunk_apply(ctypes.byref(shape), _dt(dt), _ptr(Z), _ptr(Wc), _ptr(O), _stream(dev)),
+    _check(lib().ttt_chunk_apply(ctypes.byref(shape), _dt(dt), _ptr(Zt), _ptr(Wc), _ptr(O), _stream(dev)),
            "ttt_chunk_apply")
     return O
 

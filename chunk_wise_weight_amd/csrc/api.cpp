@@ -67,8 +67,10 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   p->off_Z = p->off_Y = p->off_WtT = p->off_Zt = p->off_Vt = p->off_Wc = p->off_dW = p->off_Wp = p->off_Tot = 0;
   p->off_Rt = p->off_Wsh = 0;
   if (producers) {
-    p->off_Z = off;
-    off += align_up(BN * p->f * p->esz);
+    if (mode == TTT_MODE_MSE) {      // the MSE apply reads Z row-major; the dot apply reads Zt
+      p->off_Z = off;
+      off += align_up(BN * p->f * p->esz);
+    }
     p->off_Y = off;
     off += align_up(BN * p->d * p->esz);
     p->off_WtT = off;
@@ -116,9 +118,8 @@ inline float target_scale(const Plan& p, int mode, float eta) {
   return (mode == TTT_MODE_DOT && p.fused) ? eta : 1.0f;
 }
 
-// The chunk loop, given Z [B, n, f] (for the apply) and its token-contiguous
-// copies Zt [B, f, n], Vt [B, d, n] (for the updates; Vt scaled by
-// target_scale).
+// The chunk loop, given the token-contiguous Zt [B, f, n] and Vt [B, d, n] (Vt
+// scaled by target_scale), and for the MSE apply Z [B, n, f] as well.
 template <typename T>
 int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Ztv, const void* Vtv, const void* W0v,
              void* Ov, float* Wf, char* ws, hipStream_t s) {
@@ -152,7 +153,7 @@ int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Ztv
     if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, df, eta, s));
   }
   if (st != TTT_OK) return st;
-  return dev(ttt::launch_apply<T>(Z, Wc, (int64_t)k * df, df, O, B, n, d, f, C, s));
+  return dev(ttt::launch_apply<T>(Zt, Wc, (int64_t)k * df, df, O, B, n, d, f, C, s));
 }
 
 // Z, Zt and Vt from the producers' inputs.
@@ -182,7 +183,7 @@ inline bool finite(float x) { return isfinite(x); }
 template <typename T>
 int layer(const Plan& p, int mode, float eta, const void* H, const void* X0, const void* Wg, const void* Wu,
           const void* W0, const void* Wt, const void* cw, void* O, float* Wf, char* ws, hipStream_t s) {
-  T* Z = (T*)(ws + p.off_Z);
+  T* Z = mode == TTT_MODE_MSE ? (T*)(ws + p.off_Z) : nullptr;
   T* Zt = (T*)(ws + p.off_Zt);
   T* Vt = (T*)(ws + p.off_Vt);
   int st = run_producers<T>(p, H, X0, Wg, Wu, Wt, cw, ws, Z, Zt, Vt, target_scale(p, mode, eta), s);
@@ -416,18 +417,18 @@ int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void*
                                                   (float*)Wc, W_final, (float*)Wp, Tot, B, n, d, f, C, S, s));
 }
 
-int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Wc, void* O, void* stream) {
+int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Zt, const void* Wc, void* O, void* stream) {
   int st = check_inplace_shape(shape, dtype);
   if (st != TTT_OK) return st;
   if (shape->batch * shape->seq_len == 0) return TTT_OK;
-  if (!ok_ptr(Z) || !ok_ptr(Wc) || !ok_ptr(O)) return TTT_ERR_ARG;
+  if (!ok_ptr(Zt) || !ok_ptr(Wc) || !ok_ptr(O)) return TTT_ERR_ARG;
   hipStream_t s = (hipStream_t)stream;
   const int B = (int)shape->batch, n = (int)shape->seq_len, d = (int)shape->d_model, f = (int)shape->d_ff,
             C = (int)shape->chunk;
   const int64_t df = (int64_t)d * f, k = n / C;
   if (dtype == TTT_BF16)
-    return dev(ttt::launch_apply<bf16>((const bf16*)Z, (const bf16*)Wc, k * df, df, (bf16*)O, B, n, d, f, C, s));
-  return dev(ttt::launch_apply<float>((const float*)Z, (const float*)Wc, k * df, df, (float*)O, B, n, d, f, C, s));
+    return dev(ttt::launch_apply<bf16>((const bf16*)Zt, (const bf16*)Wc, k * df, df, (bf16*)O, B, n, d, f, C, s));
+  return dev(ttt::launch_apply<float>((const float*)Zt, (const float*)Wc, k * df, df, (float*)O, B, n, d, f, C, s));
 }
 
 // ------------------------------------------------------------------ LaCT

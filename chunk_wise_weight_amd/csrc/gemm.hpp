@@ -160,6 +160,110 @@ struct DmaOp {
                                                kb < kbytes ? off[i] + kb : kOOB, 0, 0, 0);
     }
   }
+  // Fragment of the 16 tile rows m0 + (0..15) for k group g: one 16-byte read.
+  static constexpr int kReads = 1;                // LDS read instructions per fragment
+  __device__ static __forceinline__ u32x4 frag(const char* t, int m0, int g) {
+    const int lane = lane_id();
+    return *reinterpret_cast<const u32x4*>(t + lds_off(m0 + (lane & 15), 4 * g + (lane >> 4)));
+  }
+};
+
+// Transposing 8-byte LDS read (ds_read_b64_tr_b16).  It is reached through a
+// restrict-qualified pointer so that it carries alias-scope metadata: without
+// any, the compiler's wait insertion takes it to alias every LDS-DMA write in
+// flight and holds it until the next stage's prefetch has landed (the ordinary
+// fragment reads carry type-based alias information and are not held back).
+// The stage it reads was completed by the previous step's DMA wait and barrier.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* __restrict__ p) {
+  typedef __attribute__((address_space(3))) s16x4* lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4)(p));
+}
+
+// MN-major operand: the matrix holds one k index per row (pitch ld_bytes) with
+// the tile's COLS m indices contiguous, e.g. a token-contiguous copy read by a
+// contraction over the other dimension.  A K step of KR = 128 / sizeof(T) rows
+// lands in LDS as KR rows of RB = COLS * sizeof(T) bytes (the same 128 B per m
+// index as the K-major layout), chunk c of row r in slot c ^ swz(r).
+//
+// Fragments come back in the K-major operand's register layout (lane l: m =
+// m0 + (l & 15), k = 8 (l >> 4) + (0..7) of group g for bf16, 4 (l >> 4) +
+// (0..3) for fp32):
+//  - bf16: ds_read_b64_tr_b16 transposes, within each 16-lane group, the 16 x 4
+//    matrix of 16-bit values the group's lanes address (lane j's 8 bytes are
+//    its row j) into lane j <- column j: output lane j, element e is element
+//    j & 3 of input lane 4 e + (j >> 2).  Input lane j of group h therefore
+//    addresses k row 8 h + (j >> 2) at m0 + 4 (j & 3); a second read 4 rows
+//    further down gives elements 4..7.  The LDS serves 32 lanes (256 B) per
+//    cycle: rows {0..3, 8..11} + 32 g (or + 4) at one 32-byte span, which
+//    swz(r) = 2 (r & 3) + 8 ((r >> 3) & 1) places in 8 different 32-byte
+//    bank groups.
+//  - fp32: four 4-byte reads of rows 16 g + 4 (l >> 4) + e at column m0 +
+//    (l & 15); swz(r) = 4 ((r >> 2) & 3) puts the four 16-lane groups (rows 4
+//    apart) in different 64-byte bank quarters.
+// The DMA reaches the layout by letting lane L fetch chunk slot(L) ^ swz(row).
+// The resource is rebuilt for every K step at that step's first row, so the
+// matrix may span more than the 2 GiB one resource covers.
+template <typename T, int NW, int COLS>
+struct DmaOpMN {
+  static constexpr int KR = 128 / (int)sizeof(T);       // k rows per K step
+  static constexpr int RB = COLS * (int)sizeof(T);      // LDS bytes per k row
+  static constexpr int RPI = 1024 / RB;                 // k rows per DMA instruction
+  static constexpr int NI = KR / (RPI * NW);            // DMA instructions per wave and step
+  static_assert(RPI >= 1 && RPI * RB == 1024 && NI >= 1 && NI * RPI * NW == KR, "one step splits evenly");
+  static constexpr int EPP = 16 / (int)sizeof(T);       // elements per 16-byte chunk
+  const char* base;
+  uint64_t ld;
+  int krows;                                            // k rows of the matrix (K extent)
+  unsigned off[NI];                                     // offset of this lane's chunk in its row of the step, or kOOB
+  int row[NI];                                          // k row within the step
+
+  __device__ static __forceinline__ int swz(int r) {
+    return sizeof(T) == 2 ? 2 * (r & 3) + 8 * ((r >> 3) & 1) : 4 * ((r >> 2) & 3);
+  }
+  // cols_valid (a multiple of EPP): m indices inside the matrix; krows_: K extent.
+  __device__ __forceinline__ void init(const void* base_, int cols_valid, uint64_t ld_bytes, int krows_) {
+    base = static_cast<const char*>(base_);
+    ld = ld_bytes;
+    krows = krows_;
+    const int w = wave_id(), L = lane_id();
+    constexpr int LPR = 64 / RPI;                       // lanes per k row of an instruction
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      row[i] = (w * NI + i) * RPI + L / LPR;
+      const int c = (L % LPR) ^ swz(row[i]);
+      off[i] = c * EPP < cols_valid ? (unsigned)(row[i] * ld_bytes) + (unsigned)(c * 16) : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(int ks, char* tile) const {
+    const int w = wave_id();
+    const int k0 = ks * KR;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (uint64_t)k0 * ld, (uint64_t)KR * ld);
+    char* dst = tile + w * NI * 1024;
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst + i * 1024), 16,
+                                               k0 + row[i] < krows ? off[i] : kOOB, 0, 0, 0);
+  }
+  static constexpr int kReads = sizeof(T) == 2 ? 2 : 4;
+  __device__ static __forceinline__ u32x4 frag(const char* t, int m0, int g) {
+    const int lane = lane_id(), h = lane >> 4, j = lane & 15;
+    if constexpr (sizeof(T) == 2) {
+      const int r = 32 * g + 8 * h + (j >> 2);
+      const int byte = 2 * m0 + 8 * (j & 3);
+      const char* p = t + r * RB + ((((byte >> 4) ^ swz(r))) << 4) + (byte & 15);
+      const s16x4 a = lds_read_tr16(p);
+      const s16x4 b = lds_read_tr16(p + 4 * RB);      // swz(r + 4) == swz(r)
+      const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+      return u32x4{ua[0], ua[1], ub[0], ub[1]};
+    } else {
+      const int r = 16 * g + 4 * h;                        // rows r .. r + 3, all with swizzle 4 h
+      const int byte = 4 * (m0 + j);
+      const char* p = t + r * RB + ((((byte >> 4) ^ swz(r))) << 4) + (byte & 15);
+      return u32x4{*reinterpret_cast<const unsigned*>(p), *reinterpret_cast<const unsigned*>(p + RB),
+                   *reinterpret_cast<const unsigned*>(p + 2 * RB), *reinterpret_cast<const unsigned*>(p + 3 * RB)};
+    }
+  }
 };
 
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -178,16 +282,14 @@ __device__ __forceinline__ void mma(f32x4& acc, u32x4 p, u32x4 q, float*) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(p[e]), __uint_as_float(q[e]), acc, 0, 0, 0);
 }
 
-template <class C, class PF, class QF>
+template <class C, class OP, class OQ, class PF, class QF>
 __device__ __forceinline__ void load_frags(const char* tp, const char* tq, int g, PF& pf, QF& qf) {
-  const int lane = lane_id(), w = wave_id();
-  const int prow = (w / C::WQ) * (C::BM * C::NPB) + (lane & 15);
-  const int qrow = (w % C::WQ) * (C::BM * C::NQB) + (lane & 15);
-  const int chunk = 4 * g + (lane >> 4);
+  const int w = wave_id();
+  const int pm = (w / C::WQ) * (C::BM * C::NPB), qm = (w % C::WQ) * (C::BM * C::NQB);
 #pragma unroll
-  for (int i = 0; i < C::NPB; ++i) pf[i] = *reinterpret_cast<const u32x4*>(tp + lds_off(prow + C::BM * i, chunk));
+  for (int i = 0; i < C::NPB; ++i) pf[i] = OP::frag(tp, pm + C::BM * i, g);
 #pragma unroll
-  for (int j = 0; j < C::NQB; ++j) qf[j] = *reinterpret_cast<const u32x4*>(tq + lds_off(qrow + C::BM * j, chunk));
+  for (int j = 0; j < C::NQB; ++j) qf[j] = OQ::frag(tq, qm + C::BM * j, g);
 }
 
 // One K step (two groups of 32 k for bf16 / 16 k for fp32).  Only group 0's
@@ -195,16 +297,16 @@ __device__ __forceinline__ void load_frags(const char* tp, const char* tq, int g
 // over group 0's MFMAs (two MFMAs, then one read), so that the eight waves of
 // a workgroup, which leave the step barrier together, do not all stall on one
 // burst of LDS reads.  Scheduling fences keep the compiler to that order.
-template <typename T, class C, class Acc>
+template <typename T, class C, class OP, class OQ, class Acc>
 __device__ __forceinline__ void compute_stage(const char* tp, const char* tq, Acc& acc) {
-  constexpr int NR = C::NPB + C::NQB;              // fragment reads per group
+  constexpr int NR = C::NPB * OP::kReads + C::NQB * OQ::kReads;   // LDS reads per group
   constexpr int NM = C::NPB * C::NQB;              // MFMAs per group (x4 for fp32)
   constexpr int MPM = sizeof(T) == 2 ? 1 : 4;      // MFMA instructions per block and group
   static_assert(2 * NR <= NM * MPM, "enough MFMAs to cover the next group's reads");
   u32x4 pf[2][C::NPB], qf[2][C::NQB];
-  load_frags<C>(tp, tq, 0, pf[0], qf[0]);
+  load_frags<C, OP, OQ>(tp, tq, 0, pf[0], qf[0]);
   __builtin_amdgcn_sched_barrier(0);
-  load_frags<C>(tp, tq, 1, pf[1], qf[1]);
+  load_frags<C, OP, OQ>(tp, tq, 1, pf[1], qf[1]);
 #pragma unroll
   for (int i = 0; i < C::NPB; ++i)
 #pragma unroll
@@ -259,7 +361,7 @@ __device__ __forceinline__ void mainloop(const OP& op, const OQ& oq, int nks, Ac
       op.issue(ks + 1, nxt);
       oq.issue(ks + 1, nxt + C::PBytes);
     }
-    compute_stage<T, C>(cur, cur + C::PBytes, acc);
+    compute_stage<T, C, OP, OQ>(cur, cur + C::PBytes, acc);
     wait_dma();
     __syncthreads();
     hook(ks, acc, cur);

@@ -449,9 +449,11 @@ __global__ __launch_bounds__(256) void k_scan_fixup(T* __restrict__ Wc, const T*
 // ------------------------------------------------------------------ apply
 
 // O_c = Z_c W^T for every chunk (eq. (3)).  P = d_model rows of W, Q = the
-// chunk's tokens, K = d_ff.  W of (b, c) is W + b * wsb + c * wsc.
+// chunk's tokens, K = d_ff.  W of (b, c) is W + b * wsb + c * wsc.  Z is read
+// from its token-contiguous copy Zt [B, f, n] (the one the updates contract
+// over) as an MN-major operand, so no row-major copy of Z is needed.
 template <typename T>
-TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Z, const T* __restrict__ W, int64_t wsb, int64_t wsc,
+TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict__ W, int64_t wsb, int64_t wsc,
                                    T* __restrict__ O, int n, int d, int f, int C_) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
@@ -468,10 +470,10 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Z, const T* __restrict_
   const uint64_t ldb = (uint64_t)f * esz<T>();
 
   DmaOp<G::NW, G::BP> op;
-  DmaOp<G::NW, G::BQ> oq;
+  DmaOpMN<T, G::NW, G::BQ> oq;
   op.init(W + (int64_t)b * wsb + (int64_t)c * wsc + (int64_t)i0 * f, nullptr, min(G::BP, d - i0), ldb,
           (unsigned)ldb);
-  oq.init(Z + row0 * f, nullptr, min(G::BQ, C_ - t0), ldb, (unsigned)ldb);
+  oq.init(Zt + (int64_t)b * f * n + (int64_t)c * C_ + t0, min(G::BQ, C_ - t0), (uint64_t)n * esz<T>(), f);
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
@@ -704,11 +706,11 @@ hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc
 }
 
 template <typename T>
-hipError_t launch_apply(const T* Z, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int Cs,
+hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int Cs,
                         hipStream_t s) {
   const int64_t tiles = cdiv(d, kWB) * cdiv(Cs, kWB) * B * (n / Cs);
   if (tiles == 0) return hipSuccess;
-  k_apply<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Z, W, wsb, wsc, O, n, d, f, Cs);
+  k_apply<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, W, wsb, wsc, O, n, d, f, Cs);
   return hipGetLastError();
 }
 

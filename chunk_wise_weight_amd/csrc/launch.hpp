@@ -41,7 +41,7 @@ inline int update_scan_segments(int64_t d, int64_t f, int64_t k) {
   return S;
 }
 template <typename T>
-hipError_t launch_apply(const T* Z, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
+hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
                         hipStream_t s);
 template <typename T>
 hipError_t launch_mse_chunk(const T* Z, const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,

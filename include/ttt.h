@@ -186,9 +186,10 @@ int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void*
                           const void* Vt, void* Wc, float* W_final, void* workspace, size_t workspace_bytes,
                           void* stream);
 
-/* Apply (eq. (3)): O [B, n, d], O_c = Z_c Wc[b, c]^T with Z [B, n, f] and
- * Wc [B, k, d, f] dtype. */
-int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Z, const void* Wc, void* O,
+/* Apply (eq. (3)): O [B, n, d], O_c = Z_c Wc[b, c]^T, with Z given as its
+ * token-contiguous copy Zt [B, f, n] (the one the updates read; the kernel
+ * contracts over f by transposing tiles in LDS) and Wc [B, k, d, f] dtype. */
+int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Zt, const void* Wc, void* O,
                     void* stream);
 
 /* ------------------------------------------------------------------ LaCT SwiGLU layer */

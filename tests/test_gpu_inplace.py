@@ -88,10 +88,10 @@ def _t(x):
 def test_delta_scan_apply_steps(dtype):
     B, n, d, f, C, eta = 2, 768, 264, 392, 192, 0.02
     Z, V, W0 = _zv(dtype, B, n, d, f, 11)
-    Zg, Wg = Z.cuda(), W0.cuda()
+    Wg = W0.cuda()
     dW = cw.ttt_chunk_delta(_t(Z).cuda(), _t(V).cuda(), C)
     Wc, Wf = cw.ttt_chunk_scan(dW, Wg, eta, C, n)
-    O = cw.ttt_chunk_apply(Zg, Wc, C)
+    O = cw.ttt_chunk_apply(_t(Z).cuda(), Wc, C)
     torch.cuda.synchronize()
     Zn, Vn, W0n = f64(Z), f64(V), f64(W0)
     k = n // C
@@ -236,7 +236,7 @@ def test_step_composition_equals_full_call():
     Z, Zt = cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"])
     Vt = cw.ttt_produce_vhat(g["X0"], g["conv_w"], g["W_target"], scale=cfg.eta)
     Wc, Wf2 = cw.ttt_chunk_update_scan(Zt, Vt, g["W_down0"], cfg.chunk)
-    O2 = cw.ttt_chunk_apply(Z, Wc, cfg.chunk)
+    O2 = cw.ttt_chunk_apply(Zt, Wc, cfg.chunk)
     torch.cuda.synchronize()
     assert torch.equal(O, O2) and torch.equal(Wf, Wf2)
     # the chunk loop alone, from Z and V^ in their natural layouts
