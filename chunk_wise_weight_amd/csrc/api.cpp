@@ -25,8 +25,8 @@ struct Plan {
   size_t esz;
   bool fused;
   int S;              // sequence segments of the fused update-scan
-  // workspace regions (byte offsets); Z, Y and WtT only with the producers
-  size_t off_Z, off_Y, off_WtT, off_Zt, off_Vt, off_Wc, off_dW, off_Wp, off_Tot, off_Rt, off_Wsh, total;
+  // workspace regions (byte offsets); Y and WtT only with the producers
+  size_t off_Y, off_WtT, off_Zt, off_Vt, off_Wc, off_dW, off_Wp, off_Tot, off_Rt, off_Wsh, total;
 };
 
 int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
@@ -64,13 +64,9 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   const size_t BN = (size_t)p->B * p->n, DF = (size_t)p->d * p->f;
   size_t off = 0;
   p->S = p->fused ? ttt::update_scan_segments(p->d, p->f, p->k) : 1;
-  p->off_Z = p->off_Y = p->off_WtT = p->off_Zt = p->off_Vt = p->off_Wc = p->off_dW = p->off_Wp = p->off_Tot = 0;
+  p->off_Y = p->off_WtT = p->off_Zt = p->off_Vt = p->off_Wc = p->off_dW = p->off_Wp = p->off_Tot = 0;
   p->off_Rt = p->off_Wsh = 0;
   if (producers) {
-    if (mode == TTT_MODE_MSE) {      // the MSE apply reads Z row-major; the dot apply reads Zt
-      p->off_Z = off;
-      off += align_up(BN * p->f * p->esz);
-    }
     p->off_Y = off;
     off += align_up(BN * p->d * p->esz);
     p->off_WtT = off;
@@ -119,11 +115,11 @@ inline float target_scale(const Plan& p, int mode, float eta) {
 }
 
 // The chunk loop, given the token-contiguous Zt [B, f, n] and Vt [B, d, n] (Vt
-// scaled by target_scale), and for the MSE apply Z [B, n, f] as well.
+// scaled by target_scale).  Every contraction over f reads Zt as well, by
+// transposing tiles in LDS, so no row-major Z is needed.
 template <typename T>
-int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Ztv, const void* Vtv, const void* W0v,
-             void* Ov, float* Wf, char* ws, hipStream_t s) {
-  const T* Z = (const T*)Zv;
+int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vtv, const void* W0v, void* Ov,
+             float* Wf, char* ws, hipStream_t s) {
   const T* Zt = (const T*)Ztv;
   const T* Vt = (const T*)Vtv;
   const T* W0 = (const T*)W0v;
@@ -137,7 +133,7 @@ int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Ztv
     T* Wsh = p.esz == 2 ? (T*)(ws + p.off_Wsh) : nullptr;
     const T* Wcur = p.esz == 2 ? (const T*)Wsh : (const T*)(const void*)Wf;
     for (int c = 0; c < k; ++c) {
-      int st = dev(ttt::launch_mse_chunk<T>(Z, Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, B, n, d, f, C, c, eta, s));
+      int st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, B, n, d, f, C, c, eta, s));
       if (st != TTT_OK) return st;
     }
     return TTT_OK;
@@ -156,16 +152,16 @@ int run_core(const Plan& p, int mode, float eta, const void* Zv, const void* Ztv
   return dev(ttt::launch_apply<T>(Zt, Wc, (int64_t)k * df, df, O, B, n, d, f, C, s));
 }
 
-// Z, Zt and Vt from the producers' inputs.
+// Zt and Vt from the producers' inputs.
 template <typename T>
 int run_producers(const Plan& p, const void* H, const void* X0, const void* Wg, const void* Wu, const void* Wt,
-                  const void* cw, char* ws, T* Z, T* Zt, T* Vt, float vscale, hipStream_t s) {
+                  const void* cw, char* ws, T* Zt, T* Vt, float vscale, hipStream_t s) {
   const int64_t rows = p.B * p.n;
   if (rows == 0) return TTT_OK;
   const int n = (int)p.n, d = (int)p.d, f = (int)p.f;
   T* Y = (T*)(ws + p.off_Y);
   T* WtT = (T*)(ws + p.off_WtT);
-  int st = dev(ttt::launch_produce_z<T>((const T*)H, (const T*)Wg, (const T*)Wu, Z, Zt, rows, n, d, f, s));
+  int st = dev(ttt::launch_produce_z<T>((const T*)H, (const T*)Wg, (const T*)Wu, nullptr, Zt, rows, n, d, f, s));
   if (st == TTT_OK) st = dev(ttt::launch_conv<T>((const T*)X0, (const T*)cw, Y, rows, n, d, (int)p.K, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Wt, WtT, 1, d, d, 1.0f, s));
   if (st == TTT_OK) st = dev(ttt::launch_produce_vhat<T>(Y, WtT, Vt, rows, n, d, vscale, s));
@@ -183,12 +179,11 @@ inline bool finite(float x) { return isfinite(x); }
 template <typename T>
 int layer(const Plan& p, int mode, float eta, const void* H, const void* X0, const void* Wg, const void* Wu,
           const void* W0, const void* Wt, const void* cw, void* O, float* Wf, char* ws, hipStream_t s) {
-  T* Z = mode == TTT_MODE_MSE ? (T*)(ws + p.off_Z) : nullptr;
   T* Zt = (T*)(ws + p.off_Zt);
   T* Vt = (T*)(ws + p.off_Vt);
-  int st = run_producers<T>(p, H, X0, Wg, Wu, Wt, cw, ws, Z, Zt, Vt, target_scale(p, mode, eta), s);
+  int st = run_producers<T>(p, H, X0, Wg, Wu, Wt, cw, ws, Zt, Vt, target_scale(p, mode, eta), s);
   if (st != TTT_OK) return st;
-  return run_core<T>(p, mode, eta, Z, Zt, Vt, W0, O, Wf, ws, s);
+  return run_core<T>(p, mode, eta, Zt, Vt, W0, O, Wf, ws, s);
 }
 
 template <typename T>
@@ -200,7 +195,7 @@ int core(const Plan& p, int mode, float eta, const void* Z, const void* V, const
   if (st == TTT_OK)
     st = dev(ttt::launch_transpose<T>((const T*)V, Vt, (int)p.B, (int)p.n, (int)p.d, target_scale(p, mode, eta), s));
   if (st != TTT_OK) return st;
-  return run_core<T>(p, mode, eta, Z, Zt, Vt, W0, O, Wf, ws, s);
+  return run_core<T>(p, mode, eta, Zt, Vt, W0, O, Wf, ws, s);
 }
 
 }  // namespace

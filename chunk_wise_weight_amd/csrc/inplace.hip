@@ -502,76 +502,39 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
 // ------------------------------------------------------------------ MSE objective
 
 // Apply of chunk c with the current state and the residual of its squared error:
-// O_c = Z_c W^T, Rt[b] = (O_c - V^_c)^T [B, d, C].  P = the chunk's tokens,
-// Q = d_model rows of W (W_down0 for c == 0, else this row's state copy).
+// O_c = Z_c W^T, Rt[b] = (O_c - V^_c)^T [B, d, C].  P = d_model rows of W
+// (W_down0 for c == 0, else this row's state copy), Q = the chunk's tokens, read
+// from Zt [B, f, n] as an MN-major operand, K = d_ff.
 template <typename T>
-TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Z, const T* __restrict__ W, int64_t wsb,
+TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __restrict__ W, int64_t wsb,
                                        T* __restrict__ O, const T* __restrict__ Vt, T* __restrict__ Rt, int n, int d,
                                        int f, int C_, int c) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
-  const int TP = (C_ + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
+  const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int b = id / per;
   int tp, tq;
   grouped_tile(id - b * per, TP, TQ, 4, tp, tq);
-  const int t0 = tp * G::BP, i0 = tq * G::BQ;
-  const int64_t row0 = (int64_t)b * n + (int64_t)c * C_;
+  const int i0 = tp * G::BP, t0 = tq * G::BQ;
+  const int64_t row0 = (int64_t)b * n + (int64_t)c * C_ + t0;
   const uint64_t ldb = (uint64_t)f * esz<T>();
 
   DmaOp<G::NW, G::BP> op;
-  DmaOp<G::NW, G::BQ> oq;
-  op.init(Z + (row0 + t0) * f, nullptr, min(G::BP, C_ - t0), ldb, (unsigned)ldb);
-  oq.init(W + (int64_t)b * wsb + (int64_t)i0 * f, nullptr, min(G::BQ, d - i0), ldb, (unsigned)ldb);
+  DmaOpMN<T, G::NW, G::BQ> oq;
+  op.init(W + (int64_t)b * wsb + (int64_t)i0 * f, nullptr, min(G::BP, d - i0), ldb, (unsigned)ldb);
+  oq.init(Zt + (int64_t)b * f * n + (int64_t)c * C_ + t0, min(G::BQ, C_ - t0), (uint64_t)n * esz<T>(), f);
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
   static_assert(G::GPB == 1, "one accumulator group per block");
-  const int tn = min(G::BP, C_ - t0), in_ = min(G::BQ, d - i0);
-  constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem;
+  const int tn = min(G::BQ, C_ - t0), in_ = min(G::BP, d - i0);
 
   // O [token, channel]: staged as [token][channel], in passes over token rows
   {
-    constexpr int RPP = G::BP / PASSES;
-    const Staged<T, G::BQ> st{smem};
-#pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-#pragma unroll
-      for (int ib = 0; ib < G::NPB; ++ib) {
-        const int p = G::acc_p(ib, 0) - ps * RPP;
-        if (p < 0 || p >= RPP) continue;
-#pragma unroll
-        for (int j = 0; j < G::NQB; ++j)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) st.put1(p + e, G::acc_q(j), acc[ib][j][e]);
-      }
-      __syncthreads();
-      st.template flush<G::NT>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
-        return col < in_ ? O + (row0 + t0 + ps * RPP + r) * d + i0 + col : nullptr;
-      });
-      __syncthreads();
-    }
-  }
-  // residual in place: R = O - V^ (fp32), then Rt [b, channel, token] staged as
-  // [channel][token] in passes over channel rows
-  // (branch-free: a lane outside the matrix reads the nearest valid element,
-  // whose result is never stored)
-#pragma unroll
-  for (int j = 0; j < G::NQB; ++j) {
-    const int i = min(i0 + G::acc_q(j), d - 1);
-#pragma unroll
-    for (int ib = 0; ib < G::NPB; ++ib) {
-      const int t = min(t0 + G::acc_p(ib, 0), C_ - 4);
-      const f32x4 v = load4(Vt + ((int64_t)b * d + i) * n + (int64_t)c * C_ + t);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[ib][j][e] -= v[e];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  {
-    constexpr int RPP = G::BQ / PASSES;
+    constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
     const Staged<T, G::BP> st{smem};
 #pragma unroll
     for (int ps = 0; ps < PASSES; ++ps) {
@@ -580,13 +543,51 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Z, const T* __restr
         const int q = G::acc_q(j) - ps * RPP;
         if (q < 0 || q >= RPP) continue;
 #pragma unroll
-        for (int ib = 0; ib < G::NPB; ++ib)
-          st.put4(q, G::acc_p(ib, 0), acc[ib][j][0], acc[ib][j][1], acc[ib][j][2], acc[ib][j][3]);
+        for (int i = 0; i < G::NPB; ++i)
+          st.put4(q, G::acc_p(i, 0), acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
       }
       __syncthreads();
-      st.template flush<G::NT>(max(0, min(RPP, in_ - ps * RPP)), [&](int r, int col) -> T* {
-        return col < tn ? Rt + ((int64_t)b * d + i0 + ps * RPP + r) * C_ + t0 + col : nullptr;
+      st.template flush<G::NT>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
+        return col < in_ ? O + (row0 + ps * RPP + r) * d + i0 + col : nullptr;
       });
+      __syncthreads();
+    }
+  }
+  // Rt [b, channel, token] = O - V^ in fp32: the accumulators are staged as
+  // fp32 [channel][token] rows (in passes over channels); each thread then
+  // takes 8 consecutive tokens of one channel, reads V^ from Vt in one or two
+  // 16-byte pieces, subtracts and writes the same span of Rt.
+  {
+    constexpr int RPP = G::Smem / (G::BQ * 4);        // channel rows per pass
+    constexpr int PASSES = G::BP / RPP;
+    constexpr int SPANS = G::BQ / 8;                  // 8-token spans per row
+    const Staged<float, G::BQ> st{smem};
+    const T* vt = Vt + ((int64_t)b * d + i0) * n + (int64_t)c * C_ + t0;
+    T* rt = Rt + ((int64_t)b * d + i0) * C_ + t0;
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps) {
+#pragma unroll
+      for (int i = 0; i < G::NPB; ++i) {
+        const int p = G::acc_p(i, 0) - ps * RPP;
+        if (p < 0 || p >= RPP) continue;
+#pragma unroll
+        for (int j = 0; j < G::NQB; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) st.put1(p + e, G::acc_q(j), acc[i][j][e]);
+      }
+      __syncthreads();
+      const int rows = max(0, min(RPP, in_ - ps * RPP));
+      for (int idx = threadIdx.x; idx < rows * SPANS; idx += G::NT) {
+        const int r = idx / SPANS, t = (idx - r * SPANS) * 8;
+        if (t >= tn) continue;                          // tn % 8 == 0
+        const int64_t ch = ps * RPP + r;
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(smem + st.off(r, t));
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(smem + st.off(r, t + 4));
+        const f32x4 v0 = load4(vt + ch * n + t), v1 = load4(vt + ch * n + t + 4);
+        T* dst = rt + ch * C_ + t;
+        store4(dst, o0[0] - v0[0], o0[1] - v0[1], o0[2] - v0[2], o0[3] - v0[3]);
+        store4(dst + 4, o1[0] - v1[0], o1[1] - v1[1], o1[2] - v1[2], o1[3] - v1[3]);
+      }
       __syncthreads();
     }
   }
@@ -715,13 +716,13 @@ hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O,
 }
 
 template <typename T>
-hipError_t launch_mse_chunk(const T* Z, const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
+hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
                             T* Rt, int B, int n, int d, int f, int Cs, int c, float eta, hipStream_t s) {
   const int64_t df = (int64_t)d * f;
   // the state chunk c is applied with: W_down0 (shared) for c == 0, else this row's copy
   const T* W = (c == 0) ? W0 : Wcur;
   const int64_t wsb = (c == 0) ? 0 : df;
-  k_mse_apply<T><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Z, W, wsb, O, Vt, Rt, n, d, f, Cs, c);
+  k_mse_apply<T><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, W, wsb, O, Vt, Rt, n, d, f, Cs, c);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, n, d, f, Cs, c,
@@ -742,7 +743,7 @@ hipError_t launch_mse_chunk(const T* Z, const T* Zt, const T* Vt, const T* W0, c
                                                   int, int, int, int, int, hipStream_t);                          \
   template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int,          \
                                       hipStream_t);                                                               \
-  template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, const T*, float*, T*, T*, T*,   \
+  template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
                                           int, int, int, int, int, int, float, hipStream_t);
 TTT_INST(float)
 TTT_INST(bf16)

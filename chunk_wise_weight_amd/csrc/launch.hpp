@@ -44,7 +44,7 @@ template <typename T>
 hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
                         hipStream_t s);
 template <typename T>
-hipError_t launch_mse_chunk(const T* Z, const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
+hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
                             T* Rt, int B, int n, int d, int f, int C, int c, float eta, hipStream_t s);
 
 // LaCT SwiGLU fast weight (one call runs every chunk of every (batch, head)).

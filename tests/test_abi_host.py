@@ -49,13 +49,13 @@ def test_workspace_sizes():
     k = n // C
     al = lambda x: (x + 255) // 256 * 256
     core = lambda e, B=B: al(B * n * f * e) + al(B * n * d * e)          # Zt, Vt
-    # producers: conv output and W_target^T; the row-major Z only for the MSE apply
-    prod = lambda e, mse=False: (al(B * n * f * e) if mse else 0) + al(B * n * d * e) + al(d * d * e)
+    # producers: conv output and W_target^T (Z itself is only kept token-contiguous, as Zt)
+    prod = lambda e: al(B * n * d * e) + al(d * d * e)
     st, nb = _ws(_shape(), cw.TTT_F32, cw.TTT_MODE_DOT, 1)
     assert st == cw.TTT_OK
     assert nb == prod(4) + core(4) + al(B * k * d * f * 4)
     st, nb = _ws(_shape(), cw.TTT_BF16, cw.TTT_MODE_MSE, 1)
-    assert st == cw.TTT_OK and nb == prod(2, True) + core(2) + al(C * d * 2) + al(d * f * 2)
+    assert st == cw.TTT_OK and nb == prod(2) + core(2) + al(C * d * 2) + al(d * f * 2)
     st, nb = _ws(_shape(), cw.TTT_BF16, cw.TTT_MODE_DOT_SCAN, 0)
     assert st == cw.TTT_OK and nb == core(2) + al(B * k * d * f * 2) + al(B * k * d * f * 4)
     st, nb = _ws(_shape(B=4), cw.TTT_BF16, cw.TTT_MODE_MSE, 0)
