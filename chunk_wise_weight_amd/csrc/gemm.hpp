@@ -294,15 +294,17 @@ __device__ __forceinline__ void load_frags(const char* tp, const char* tq, int g
 
 // One K step (two groups of 32 k for bf16 / 16 k for fp32).  Only group 0's
 // fragments are read before the first MFMA; group 1's LDS reads are spread
-// over group 0's MFMAs (two MFMAs, then one read), so that the eight waves of
-// a workgroup, which leave the step barrier together, do not all stall on one
+// over group 0's MFMAs (two MFMAs, then one read; one and one when both
+// operands take several reads per fragment), so that the eight waves of a
+// workgroup, which leave the step barrier together, do not all stall on one
 // burst of LDS reads.  Scheduling fences keep the compiler to that order.
 template <typename T, class C, class OP, class OQ, class Acc>
 __device__ __forceinline__ void compute_stage(const char* tp, const char* tq, Acc& acc) {
   constexpr int NR = C::NPB * OP::kReads + C::NQB * OQ::kReads;   // LDS reads per group
   constexpr int NM = C::NPB * C::NQB;              // MFMAs per group (x4 for fp32)
   constexpr int MPM = sizeof(T) == 2 ? 1 : 4;      // MFMA instructions per block and group
-  static_assert(2 * NR <= NM * MPM, "enough MFMAs to cover the next group's reads");
+  constexpr int MPR = 2 * NR <= NM * MPM ? 2 : 1;  // MFMAs issued per group-1 read
+  static_assert(MPR * NR <= NM * MPM, "enough MFMAs to cover the next group's reads");
   u32x4 pf[2][C::NPB], qf[2][C::NQB];
   load_frags<C, OP, OQ>(tp, tq, 0, pf[0], qf[0]);
   __builtin_amdgcn_sched_barrier(0);
@@ -313,10 +315,10 @@ __device__ __forceinline__ void compute_stage(const char* tp, const char* tq, Ac
     for (int j = 0; j < C::NQB; ++j) mma(acc[i][j], pf[0][i], qf[0][j], (T*)nullptr);
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);     // 2 MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);   // MFMAs
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // 1 LDS read
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, NM * MPM - 2 * NR, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NM * MPM - MPR * NR, 0);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < C::NPB; ++i)

@@ -8,13 +8,18 @@
 // covers all of them.  For one chunk step, with X the rows [Q part; K part]
 // that share the current weights (update-then-apply: queries of chunk c-1 and
 // keys of chunk c; apply-then-update: queries and keys of chunk c):
-//   fwd1   A = X W1^T, U = X W3^T, Hh = silu(A) * U        (keys: also A^T, U^T, Hh^T)
-//   fwd2   Y = Hh W2^T; queries: O = Y; keys: R = Y - V    (and R^T)
-//   dh     dH = R W2; dU = dH * silu(A); dA = dH * U * silu'(A)   (stored transposed)
+//   fwd1   A = X W1^T, U = X W3^T, Hh = silu(A) * U        (keys: A and U kept)
+//   fwd2   Y = Hh W2^T; queries: O = Y; keys: R = Y - V
+//   dh     dH = R W2; dU = dH * silu(A); dA = dH * U * silu'(A)
 //   grad   G1 = dA^T K, G3 = dU^T K, G2 = R^T Hh            (split over tokens)
 //   update W -= eta * (sum of the splits), fp32 state plus operand copies
+// Every intermediate is stored token-major ([tokens, features]); the weight
+// gradients contract over tokens by reading them as MN-major operands
+// (transposed in LDS), so no transposed copy is ever written.
 // Layouts: q, k, v, O [BH, n, dh]; W1, W3 [H, m, dh]; W2 [H, dh, m];
 // states W1f, W3f [BH, m, dh], W2f [BH, dh, m] (fp32).
+#include <type_traits>
+
 #include "gemm.hpp"
 #include "launch.hpp"
 
@@ -28,29 +33,26 @@ constexpr int kSplit = 4;              // token splits of the weight-gradient GE
 
 // Workspace layout (byte offsets), one region per buffer.
 struct LactWs {
-  size_t Kt, Hh, HhT, At, Ut, R, Rt, dAt, dUt, W1s, W3s, W2s, W2Ts, part, total;
+  size_t Hh, A, U, R, dA, dU, W1s, W3s, W2s, part, total;
 };
 
 inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
 template <typename T>
 LactWs lact_layout(int B, int H, int n, int dh, int m, int C) {
+  (void)n;
   const size_t e = sizeof(T), BH = (size_t)B * H, md = (size_t)m * dh;
   LactWs w{};
   size_t o = 0;
-  w.Kt = o;   o += al(BH * n * dh * e);           // keys, token-contiguous [BH, dh, n]
   w.Hh = o;   o += al(2 * BH * C * m * e);        // hidden of [Q part; K part] [2, BH, C, m]
-  w.HhT = o;  o += al(BH * m * C * e);            // key hidden, transposed [BH, m, C]
-  w.At = o;   o += al(BH * m * C * e);            // key pre-activations [BH, m, C]
-  w.Ut = o;   o += al(BH * m * C * e);
+  w.A = o;    o += al(BH * C * m * e);            // key pre-activations [BH, C, m]
+  w.U = o;    o += al(BH * C * m * e);
   w.R = o;    o += al(BH * C * dh * e);           // residual f(k) - v [BH, C, dh]
-  w.Rt = o;   o += al(BH * dh * C * e);           // and transposed [BH, dh, C]
-  w.dAt = o;  o += al(BH * m * C * e);
-  w.dUt = o;  o += al(BH * m * C * e);
+  w.dA = o;   o += al(BH * C * m * e);            // gate backward [BH, C, m]
+  w.dU = o;   o += al(BH * C * m * e);
   w.W1s = o;  o += al(BH * md * e);               // operand copies of the current state
   w.W3s = o;  o += al(BH * md * e);
   w.W2s = o;  o += al(BH * md * e);
-  w.W2Ts = o; o += al(BH * md * e);               // W2^T [BH, m, dh]
   w.part = o; o += al((size_t)kSplit * BH * 3 * md * 4);   // split-token gradient partials
   w.total = o;
   return w;
@@ -70,12 +72,11 @@ __host__ __device__ constexpr int cdiv_d(int a, int b) { return (a + b - 1) / b;
 
 // A = X W1^T, U = X W3^T over the rows X of both parts.  P = rows (tokens),
 // Q = W1 / W3 rows in alternating 32-row blocks.  Writes Hh [2, BH, C, m] for
-// both parts, and for the key part A^T, U^T, Hh^T [BH, m, C].
+// both parts, and for the key part A and U [BH, C, m].
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ W1s,
-                                       const T* __restrict__ W3s, T* __restrict__ Hh, T* __restrict__ HhT,
-                                       T* __restrict__ At, T* __restrict__ Ut, int BH, int n, int dh, int m, int C,
-                                       StepRows sr) {
+                                       const T* __restrict__ W3s, T* __restrict__ Hh, T* __restrict__ A,
+                                       T* __restrict__ U, int BH, int n, int dh, int m, int C, StepRows sr) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int tq_n = (m + G::BQ / 2 - 1) / (G::BQ / 2);
@@ -103,30 +104,55 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restr
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
   // Each wave's 64 Q rows are 32 W1 rows (blocks 0, 1) then the same 32 W3 rows
-  // (blocks 2, 3): block jj pairs with block jj + 2.  The outputs go through
-  // the stage area one at a time: A^T and U^T (keys), then Hh = silu(A) * U is
-  // formed in place of A, then Hh^T (keys) and Hh.
+  // (blocks 2, 3): block jj pairs with block jj + 2.  Every output is a
+  // [token][column] tile staged in LDS and copied out as whole row pieces:
+  // A and U of the keys together (one half of the stage area each, when they
+  // fit), then Hh = silu(A) * U, formed in place of A.
   static_assert(G::NQB == 4 && G::BM == 16 && G::GPB == 1, "two W1/W3 block pairs per wave");
+  using ST = Staged<T, G::BQ / 2>;
+  constexpr int TILE = G::BP * ST::RB;                           // bytes of one staged output
+  constexpr bool PAIR = 2 * TILE <= G::Smem;
   const int jl = (wave_id() % G::WQ) * 32 + (lane_id() & 15);      // local column of block jj = 0
   const int jn = min(G::BQ / 2, m - j0), tn = min(G::BP, nrows - r0);
-  // [column][token] tile of the key rows: rows j, tokens contiguous
-  auto stage_t = [&](T* dstbase, int half) {
-    const Staged<T, G::BP> st{smem};
+  // half: 0 = W1 blocks (A, later Hh), 2 = W3 blocks (U); a compile-time
+  // constant, so that the accumulators stay in registers
+  auto put = [&](char* base, auto half) __attribute__((always_inline)) {
+    const ST st{base};
 #pragma unroll
     for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
-        st.put4(jl + 16 * jj, G::acc_p(i, 0), acc[i][jj + half][0], acc[i][jj + half][1], acc[i][jj + half][2],
-                acc[i][jj + half][3]);
-    __syncthreads();
-    st.template flush<G::NT>(jn, [&](int r, int col) -> T* {
-      return col < tn ? dstbase + ((int64_t)bh * m + j0 + r) * C + r0 + col : nullptr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj + decltype(half)::value][e]);
+  };
+  using H0 = std::integral_constant<int, 0>;
+  using H2 = std::integral_constant<int, 2>;
+  auto flush = [&](char* base, T* dst) __attribute__((always_inline)) {   // dst: [C, m] block of this bh
+    const ST st{base};
+    st.template flush<G::NT>(tn, [&](int r, int col) -> T* {
+      return col < jn ? dst + (int64_t)(r0 + r) * m + j0 + col : nullptr;
     });
-    __syncthreads();
   };
   if (part) {
-    stage_t(At, 0);
-    stage_t(Ut, 2);
+    T* a_ = A + (int64_t)bh * C * m;
+    T* u_ = U + (int64_t)bh * C * m;
+    if constexpr (PAIR) {
+      put(smem, H0{});
+      put(smem + TILE, H2{});
+      __syncthreads();
+      flush(smem, a_);
+      flush(smem + TILE, u_);
+      __syncthreads();
+    } else {
+      put(smem, H0{});
+      __syncthreads();
+      flush(smem, a_);
+      __syncthreads();
+      put(smem, H2{});
+      __syncthreads();
+      flush(smem, u_);
+      __syncthreads();
+    }
   }
 #pragma unroll
   for (int i = 0; i < G::NPB; ++i)
@@ -134,33 +160,19 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restr
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[i][jj][e] = silu_f(acc[i][jj][e]) * acc[i][jj + 2][e];
-  if (part) stage_t(HhT, 0);
-  // Hh [part, bh, token, column]: staged as [token][column]
-  {
-    const Staged<T, G::BQ / 2> sz{smem};
-#pragma unroll
-    for (int i = 0; i < G::NPB; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sz.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj][e]);
-    __syncthreads();
-    T* hh = Hh + ((int64_t)part * BH + bh) * C * m;
-    sz.template flush<G::NT>(tn, [&](int r, int col) -> T* {
-      return col < jn ? hh + (int64_t)(r0 + r) * m + j0 + col : nullptr;
-    });
-  }
+  put(smem, H0{});
+  __syncthreads();
+  flush(smem, Hh + ((int64_t)part * BH + bh) * C * m);
 }
 
 // ------------------------------------------------------------------ fwd2
 
 // Y = Hh W2^T.  P = dh rows of W2s [BH, dh, m], Q = rows of Hh (both parts).
-// Query rows: O[bh, qc C + r, :] = Y.  Key rows: R = Y - V (R [BH, C, dh]) and
-// R^T [BH, dh, C].
+// Query rows: O[bh, qc C + r, :] = Y.  Key rows: R = Y - V (R [BH, C, dh]).
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __restrict__ W2s, const T* __restrict__ v,
-                                       T* __restrict__ O, T* __restrict__ R, T* __restrict__ Rt, int BH, int n, int dh,
-                                       int m, int C, StepRows sr) {
+                                       T* __restrict__ O, T* __restrict__ R, int BH, int n, int dh, int m, int C,
+                                       StepRows sr) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (dh + G::BP - 1) / G::BP;
@@ -188,8 +200,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __rest
   const int tn = min(G::BQ, nrows - r0), in_ = min(G::BP, dh - i0);
   constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
   // O (queries) or R = Y - V (keys, formed in fp32 block by block), [token][channel]:
-  // staged by token rows; for keys R^T [bh, channel, token] is copied out of the
-  // same staged (rounded) tile, transposed.
+  // staged by token rows.
   const Staged<T, G::BP> st{smem};
   T* base = part ? R + (int64_t)bh * C * dh : O + ((int64_t)bh * n + (int64_t)sr.qc * C) * dh;
 #pragma unroll
@@ -215,64 +226,81 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __rest
     st.template flush<G::NT>(rows, [&](int rr, int col) -> T* {
       return col < in_ ? base + (int64_t)(r0 + ps * RPP + rr) * dh + i0 + col : nullptr;
     });
-    if (part)
-      st.template flush_t<G::NT>(in_, rows, [&](int ci, int rr) -> T* {
-        return Rt + ((int64_t)bh * dh + i0 + ci) * C + r0 + ps * RPP + rr;
-      });
     __syncthreads();
   }
 }
 
 // ------------------------------------------------------------------ dh
 
-// dH = R W2 [C, m]; P = tokens (R rows), Q = m rows of W2^T.  Epilogue: the
-// SiLU-gate backward, written token-contiguous: dU^T = (dH * silu(A))^T,
-// dA^T = (dH * U * silu'(A))^T, silu'(a) = s (1 + a (1 - s)), s = sigmoid(a).
+// dH = R W2 [C, m]; P = m (W2s [BH, dh, m] read as an MN-major operand), Q =
+// tokens (R rows).  Epilogue, the SiLU-gate backward: dH is staged as fp32
+// [token][m] rows (in passes over tokens); each thread then takes 8
+// consecutive m of one token, reads A and U in 16-byte pieces and writes
+// dU = dH * silu(A), dA = dH * U * silu'(A), silu'(a) = s (1 + a (1 - s)),
+// s = sigmoid(a), the same way ([BH, C, m]).
 template <typename T>
-TTT_GEMM_KERNEL(Wide) void k_lact_dh(const T* __restrict__ R, const T* __restrict__ W2Ts, const T* __restrict__ At,
-                                     const T* __restrict__ Ut, T* __restrict__ dAt, T* __restrict__ dUt, int BH, int dh,
+TTT_GEMM_KERNEL(Wide) void k_lact_dh(const T* __restrict__ R, const T* __restrict__ W2s, const T* __restrict__ A,
+                                     const T* __restrict__ U, T* __restrict__ dA, T* __restrict__ dU, int BH, int dh,
                                      int m, int C, int nk) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
-  const int TP = (nk + G::BP - 1) / G::BP, TQ = (m + G::BQ - 1) / G::BQ, per = TP * TQ;
+  const int TP = (m + G::BP - 1) / G::BP, TQ = (nk + G::BQ - 1) / G::BQ, per = TP * TQ;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = id / per;
   int tp, tq;
   grouped_tile(id - bh * per, TP, TQ, 4, tp, tq);
-  const int t0 = tp * G::BP, j0 = tq * G::BQ;
+  const int j0 = tp * G::BP, t0 = tq * G::BQ;
   const uint64_t ldb = (uint64_t)dh * esz<T>();
 
-  DmaOp<G::NW, G::BP> op;
+  DmaOpMN<T, G::NW, G::BP> op;
   DmaOp<G::NW, G::BQ> oq;
-  op.init(R + ((int64_t)bh * C + t0) * dh, nullptr, min(G::BP, nk - t0), ldb, (unsigned)ldb);
-  oq.init(W2Ts + (int64_t)bh * m * dh + (int64_t)j0 * dh, nullptr, min(G::BQ, m - j0), ldb, (unsigned)ldb);
+  op.init(W2s + (int64_t)bh * dh * m + j0, min(G::BP, m - j0), (uint64_t)m * esz<T>(), dh);
+  oq.init(R + ((int64_t)bh * C + t0) * dh, nullptr, min(G::BQ, nk - t0), ldb, (unsigned)ldb);
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
+  static_assert(G::GPB == 1, "one accumulator group per block");
+  const int jn = min(G::BP, m - j0), tn = min(G::BQ, nk - t0);
+  constexpr int RPP = G::Smem / (G::BP * 4);        // token rows per pass
+  constexpr int PASSES = G::BQ / RPP;
+  constexpr int SPANS = G::BP / 8;                  // 8-column spans per row
+  const Staged<float, G::BP> st{smem};
 #pragma unroll
-  for (int jq = 0; jq < G::NQB; ++jq) {
-    const int j = j0 + G::acc_q(jq);
-    if (j >= m) continue;
-    const int64_t rowj = ((int64_t)bh * m + j) * C;
+  for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
-    for (int ib = 0; ib < G::NPB; ++ib)
+    for (int jq = 0; jq < G::NQB; ++jq) {
+      const int qq = G::acc_q(jq) - ps * RPP;
+      if (qq < 0 || qq >= RPP) continue;
 #pragma unroll
-      for (int g = 0; g < G::GPB; ++g) {
-        const int t = t0 + G::acc_p(ib, g);
-        if (t >= nk) continue;
-        const f32x4 a = load4(At + rowj + t), u = load4(Ut + rowj + t);
-        float du[4], da[4];
+      for (int ib = 0; ib < G::NPB; ++ib)
+        st.put4(qq, G::acc_p(ib, 0), acc[ib][jq][0], acc[ib][jq][1], acc[ib][jq][2], acc[ib][jq][3]);
+    }
+    __syncthreads();
+    const int rows = max(0, min(RPP, tn - ps * RPP));
+    for (int idx = threadIdx.x; idx < rows * SPANS; idx += G::NT) {
+      const int r = idx / SPANS, c = (idx - r * SPANS) * 8;
+      if (c >= jn) continue;                            // jn % 8 == 0
+      const int64_t o = ((int64_t)bh * C + t0 + ps * RPP + r) * m + j0 + c;
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(smem + st.off(r, c));
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(smem + st.off(r, c + 4));
+      const f32x4 a0 = load4(A + o), a1 = load4(A + o + 4), u0 = load4(U + o), u1 = load4(U + o + 4);
+      float du[8], da[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float dh_ = acc[ib][jq][4 * g + e];
-          const float s = sigmoid_f(a[e]);
-          du[e] = dh_ * a[e] * s;
-          da[e] = dh_ * u[e] * s * (1.0f + a[e] * (1.0f - s));
-        }
-        store4(dUt + rowj + t, du[0], du[1], du[2], du[3]);
-        store4(dAt + rowj + t, da[0], da[1], da[2], da[3]);
+      for (int e = 0; e < 8; ++e) {
+        const float g = e < 4 ? d0[e] : d1[e - 4];
+        const float a = e < 4 ? a0[e] : a1[e - 4];
+        const float u = e < 4 ? u0[e] : u1[e - 4];
+        const float s = sigmoid_f(a);
+        du[e] = g * a * s;
+        da[e] = g * u * s * (1.0f + a * (1.0f - s));
       }
+      store4(dU + o, du[0], du[1], du[2], du[3]);
+      store4(dU + o + 4, du[4], du[5], du[6], du[7]);
+      store4(dA + o, da[0], da[1], da[2], da[3]);
+      store4(dA + o + 4, da[4], da[5], da[6], da[7]);
+    }
+    __syncthreads();
   }
 }
 
@@ -280,13 +308,14 @@ TTT_GEMM_KERNEL(Wide) void k_lact_dh(const T* __restrict__ R, const T* __restric
 
 // Three contractions over the chunk's tokens, split kSplit ways along the
 // tokens, written as fp32 partials part[s][bh][w] (w = 0: G1 [m, dh], 1: G3
-// [m, dh], 2: G2 [dh, m]):
-//   G1[j][i] = sum_t dA[t][j] K[t][i]   P = i (K^T rows), Q = j (dA^T rows)
-//   G3[j][i] = sum_t dU[t][j] K[t][i]   P = i (K^T rows), Q = j (dU^T rows)
-//   G2[i][j] = sum_t R[t][i] Hh[t][j]   P = j (Hh^T rows), Q = i (R^T rows)
+// [m, dh], 2: G2 [dh, m]).  Every operand is token-major and read as an
+// MN-major operand (k = tokens):
+//   G1[j][i] = sum_t dA[t][j] K[t][i]   P = i (K columns), Q = j (dA columns)
+//   G3[j][i] = sum_t dU[t][j] K[t][i]   P = i (K columns), Q = j (dU columns)
+//   G2[i][j] = sum_t R[t][i] Hh[t][j]   P = j (Hh columns), Q = i (R columns)
 template <typename T>
-TTT_GEMM_KERNEL(Wide) void k_lact_grad(const T* __restrict__ Kt, const T* __restrict__ dAt, const T* __restrict__ dUt,
-                                       const T* __restrict__ HhT, const T* __restrict__ Rt, float* __restrict__ part,
+TTT_GEMM_KERNEL(Wide) void k_lact_grad(const T* __restrict__ k, const T* __restrict__ dA, const T* __restrict__ dU,
+                                       const T* __restrict__ Hh, const T* __restrict__ R, float* __restrict__ part,
                                        int BH, int n, int dh, int m, int C, int kc, int nk, int kslice) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
@@ -305,29 +334,23 @@ TTT_GEMM_KERNEL(Wide) void k_lact_grad(const T* __restrict__ Kt, const T* __rest
   const int p0 = tp * G::BP, q0 = tq * G::BQ;
   const int tk0 = s * kslice;
   const int kl = max(0, min(kslice, nk - tk0));
-  const unsigned kbytes = (unsigned)kl * esz<T>();
   const T* Pbase;
   const T* Qbase;
-  uint64_t pld, qld;
   if (which < 2) {
-    Pbase = Kt + ((int64_t)bh * dh + p0) * n + (int64_t)kc * C + tk0;
-    pld = (uint64_t)n * esz<T>();
-    Qbase = (which == 0 ? dAt : dUt) + ((int64_t)bh * m + q0) * C + tk0;
-    qld = (uint64_t)C * esz<T>();
+    Pbase = k + ((int64_t)bh * n + (int64_t)kc * C + tk0) * dh + p0;
+    Qbase = (which == 0 ? dA : dU) + ((int64_t)bh * C + tk0) * m + q0;
   } else {
-    Pbase = HhT + ((int64_t)bh * m + p0) * C + tk0;
-    pld = (uint64_t)C * esz<T>();
-    Qbase = Rt + ((int64_t)bh * dh + q0) * C + tk0;
-    qld = (uint64_t)C * esz<T>();
+    Pbase = Hh + ((int64_t)(BH + bh) * C + tk0) * m + p0;         // key part of Hh
+    Qbase = R + ((int64_t)bh * C + tk0) * dh + q0;
   }
-  DmaOp<G::NW, G::BP> op;
-  DmaOp<G::NW, G::BQ> oq;
-  op.init(Pbase, nullptr, min(G::BP, PD - p0), pld, kbytes);
-  oq.init(Qbase, nullptr, min(G::BQ, QD - q0), qld, kbytes);
+  DmaOpMN<T, G::NW, G::BP> op;
+  DmaOpMN<T, G::NW, G::BQ> oq;
+  op.init(Pbase, min(G::BP, PD - p0), (uint64_t)PD * esz<T>(), kl);
+  oq.init(Qbase, min(G::BQ, QD - q0), (uint64_t)QD * esz<T>(), kl);
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
-  mainloop<T, G>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
-
+  constexpr int KR = 128 / esz<T>();
+  mainloop<T, G>(op, oq, (kl + KR - 1) / KR, acc, smem, NoHook{});
   const int64_t md = (int64_t)m * dh;
   float* out = part + (((int64_t)s * BH + bh) * 3 + which) * md;
 #pragma unroll
@@ -348,13 +371,13 @@ TTT_GEMM_KERNEL(Wide) void k_lact_grad(const T* __restrict__ Kt, const T* __rest
 
 // ------------------------------------------------------------------ state update
 
-// W -= eta * sum_s part[s]; writes the fp32 state and the operand copies
-// (W2 also transposed).  Four elements per thread; grid.y = bh * 3 + w.
+// W -= eta * sum_s part[s]; writes the fp32 state and the operand copies.
+// Four elements per thread; grid.y = bh * 3 + w.
 template <typename T>
 __global__ __launch_bounds__(256) void k_lact_update(const float* __restrict__ part, float* __restrict__ W1f,
                                                      float* __restrict__ W3f, float* __restrict__ W2f,
                                                      T* __restrict__ W1s, T* __restrict__ W3s, T* __restrict__ W2s,
-                                                     T* __restrict__ W2Ts, int BH, int dh, int m, float eta) {
+                                                     int BH, int dh, int m, float eta) {
   const int64_t md = (int64_t)m * dh;
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= md) return;
@@ -368,11 +391,6 @@ __global__ __launch_bounds__(256) void k_lact_update(const float* __restrict__ p
   x -= eta * gsum;
   store4(Wf, x[0], x[1], x[2], x[3]);
   store4(Ws, x[0], x[1], x[2], x[3]);
-  if (w == 2) {   // W2 [dh, m] element e = (i, j) -> W2^T [m, dh] element (j, i)
-    const int i = (int)(e / m), j = (int)(e % m);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) W2Ts[(int64_t)bh * md + (int64_t)(j + q) * dh + i] = from_f32<T>(x[q]);
-  }
 }
 
 // Initial state of every (batch row, head) from the heads' initial weights.
@@ -381,7 +399,7 @@ __global__ __launch_bounds__(256) void k_lact_init(const T* __restrict__ W1, con
                                                    const T* __restrict__ W2, float* __restrict__ W1f,
                                                    float* __restrict__ W3f, float* __restrict__ W2f,
                                                    T* __restrict__ W1s, T* __restrict__ W3s, T* __restrict__ W2s,
-                                                   T* __restrict__ W2Ts, int H, int dh, int m) {
+                                                   int H, int dh, int m) {
   const int64_t md = (int64_t)m * dh;
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= md) return;
@@ -392,11 +410,6 @@ __global__ __launch_bounds__(256) void k_lact_init(const T* __restrict__ W1, con
   T* Ws = (w == 0 ? W1s : (w == 1 ? W3s : W2s)) + (int64_t)bh * md + e;
   store4(Wf, x[0], x[1], x[2], x[3]);
   store4(Ws, x[0], x[1], x[2], x[3]);
-  if (w == 2) {
-    const int i = (int)(e / m), j = (int)(e % m);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) W2Ts[(int64_t)bh * md + (int64_t)(j + q) * dh + i] = from_f32<T>(x[q]);
-  }
 }
 
 // ------------------------------------------------------------------ host driver
@@ -411,19 +424,15 @@ hipError_t launch_lact(const LactArgs& a, hipStream_t s) {
   const int BH = a.B * a.H, n = a.n, dh = a.dh, m = a.m, C = a.C;
   const int k = n / C;
   const LactWs L = lact_layout<T>(a.B, a.H, n, dh, m, C);
-  T* Kt = (T*)(a.ws + L.Kt);
   T* Hh = (T*)(a.ws + L.Hh);
-  T* HhT = (T*)(a.ws + L.HhT);
-  T* At = (T*)(a.ws + L.At);
-  T* Ut = (T*)(a.ws + L.Ut);
+  T* A = (T*)(a.ws + L.A);
+  T* U = (T*)(a.ws + L.U);
   T* R = (T*)(a.ws + L.R);
-  T* Rt = (T*)(a.ws + L.Rt);
-  T* dAt = (T*)(a.ws + L.dAt);
-  T* dUt = (T*)(a.ws + L.dUt);
+  T* dA = (T*)(a.ws + L.dA);
+  T* dU = (T*)(a.ws + L.dU);
   T* W1s = (T*)(a.ws + L.W1s);
   T* W3s = (T*)(a.ws + L.W3s);
   T* W2s = (T*)(a.ws + L.W2s);
-  T* W2Ts = (T*)(a.ws + L.W2Ts);
   float* part = (float*)(a.ws + L.part);
   const T* q = (const T*)a.q;
   const T* kk = (const T*)a.k;
@@ -434,10 +443,9 @@ hipError_t launch_lact(const LactArgs& a, hipStream_t s) {
   hipError_t e;
 
   k_lact_init<T><<<ew, 256, 0, s>>>((const T*)a.W1, (const T*)a.W3, (const T*)a.W2, a.W1f, a.W3f, a.W2f, W1s, W3s,
-                                    W2s, W2Ts, a.H, dh, m);
+                                    W2s, a.H, dh, m);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (n == 0) return hipSuccess;
-  if ((e = launch_transpose<T>(kk, Kt, BH, n, dh, 1.0f, s)) != hipSuccess) return e;
 
   const int kslice = (int)(cdiv(cdiv(C, kSplit), 64) * 64);
   const bool upd_first = a.order == 0;
@@ -454,23 +462,22 @@ hipError_t launch_lact(const LactArgs& a, hipStream_t s) {
       sr.nq = sr.nk = C;
     }
     const int tp1 = (int)(cdiv(sr.nq, Wide::BP) + cdiv(sr.nk, Wide::BP));
-    k_lact_fwd1<T><<<(unsigned)(tp1 * cdiv(m, Wide::BQ / 2) * BH), Wide::NT, 0, s>>>(q, kk, W1s, W3s, Hh, HhT, At, Ut,
-                                                                                   BH, n, dh, m, C, sr);
+    k_lact_fwd1<T><<<(unsigned)(tp1 * cdiv(m, Wide::BQ / 2) * BH), Wide::NT, 0, s>>>(q, kk, W1s, W3s, Hh, A, U, BH, n,
+                                                                                   dh, m, C, sr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int tq2 = (int)(cdiv(sr.nq, Wide::BQ) + cdiv(sr.nk, Wide::BQ));
-    k_lact_fwd2<T><<<(unsigned)(cdiv(dh, Wide::BP) * tq2 * BH), Wide::NT, 0, s>>>(Hh, W2s, v, O, R, Rt, BH, n, dh, m,
-                                                                                C, sr);
+    k_lact_fwd2<T><<<(unsigned)(cdiv(dh, Wide::BP) * tq2 * BH), Wide::NT, 0, s>>>(Hh, W2s, v, O, R, BH, n, dh, m, C,
+                                                                                sr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (sr.nk == 0) continue;
-    k_lact_dh<T><<<(unsigned)(cdiv(sr.nk, Wide::BP) * cdiv(m, Wide::BQ) * BH), Wide::NT, 0, s>>>(
-        R, W2Ts, At, Ut, dAt, dUt, BH, dh, m, C, sr.nk);
+    k_lact_dh<T><<<(unsigned)(cdiv(m, Wide::BP) * cdiv(sr.nk, Wide::BQ) * BH), Wide::NT, 0, s>>>(
+        R, W2s, A, U, dA, dU, BH, dh, m, C, sr.nk);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t tg = (2 * cdiv(dh, Wide::BP) * cdiv(m, Wide::BQ) + cdiv(m, Wide::BP) * cdiv(dh, Wide::BQ)) *
                        (int64_t)kSplit * BH;
-    k_lact_grad<T><<<(unsigned)tg, Wide::NT, 0, s>>>(Kt, dAt, dUt, HhT, Rt, part, BH, n, dh, m, C, sr.kc, sr.nk,
-                                                     kslice);
+    k_lact_grad<T><<<(unsigned)tg, Wide::NT, 0, s>>>(kk, dA, dU, Hh, R, part, BH, n, dh, m, C, sr.kc, sr.nk, kslice);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_lact_update<T><<<ew, 256, 0, s>>>(part, a.W1f, a.W3f, a.W2f, W1s, W3s, W2s, W2Ts, BH, dh, m, a.eta);
+    k_lact_update<T><<<ew, 256, 0, s>>>(part, a.W1f, a.W3f, a.W2f, W1s, W3s, W2s, BH, dh, m, a.eta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
