@@ -70,69 +70,78 @@ __host__ __device__ constexpr int cdiv_d(int a, int b) { return (a + b - 1) / b;
 
 // ------------------------------------------------------------------ fwd1
 
-// A = X W1^T, U = X W3^T over the rows X of both parts.  P = rows (tokens),
-// Q = W1 / W3 rows in alternating 32-row blocks.  Writes Hh [2, BH, C, m] for
-// both parts, and for the key part A and U [BH, C, m].
+// A = X W1^T, U = X W3^T over the rows X of both parts.  P = W1 / W3 rows in
+// alternating 32-row blocks (128 hidden units per tile), Q = rows (tokens),
+// so that a lane holds 4 consecutive hidden units of one token.  Writes Hh
+// [2, BH, C, m] for both parts, and for the key part A and U [BH, C, m].
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ W1s,
                                        const T* __restrict__ W3s, T* __restrict__ Hh, T* __restrict__ A,
                                        T* __restrict__ U, int BH, int n, int dh, int m, int C, StepRows sr) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
-  const int tq_n = (m + G::BQ / 2 - 1) / (G::BQ / 2);
-  const int tpq = (sr.nq + G::BP - 1) / G::BP, tpk = (sr.nk + G::BP - 1) / G::BP;
-  const int TP = tpq + tpk, per = TP * tq_n;
+  const int TP = (m + G::BP / 2 - 1) / (G::BP / 2);
+  const int tqq = (sr.nq + G::BQ - 1) / G::BQ, tqk = (sr.nk + G::BQ - 1) / G::BQ;
+  const int TQ = tqq + tqk, per = TP * TQ;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = id / per;
   int tp, tq;
-  grouped_tile(id - bh * per, TP, tq_n, 4, tp, tq);
-  const int part = tp < tpq ? 0 : 1;
-  const int r0 = (part ? tp - tpq : tp) * G::BP;
+  grouped_tile(id - bh * per, TP, TQ, 4, tp, tq);
+  const int part = tq < tqq ? 0 : 1;
+  const int r0 = (part ? tq - tqq : tq) * G::BQ;
   const int nrows = part ? sr.nk : sr.nq;
   const T* X = (part ? k : q) + ((int64_t)bh * n + (int64_t)(part ? sr.kc : sr.qc) * C) * dh;
-  const int j0 = tq * (G::BQ / 2);
+  const int j0 = tp * (G::BP / 2);
   const uint64_t ldb = (uint64_t)dh * esz<T>();
   const int64_t md = (int64_t)m * dh;
 
-  DmaOp<G::NW, G::BP> op;
-  op.init(X + (int64_t)r0 * dh, nullptr, min(G::BP, nrows - r0), ldb, (unsigned)ldb);
-  DmaOp<G::NW, G::BQ, true> oq;
-  oq.init(W1s + bh * md + (int64_t)j0 * dh, W3s + bh * md + (int64_t)j0 * dh, min(G::BQ / 2, m - j0), ldb,
+  DmaOp<G::NW, G::BP, true> op;
+  op.init(W1s + bh * md + (int64_t)j0 * dh, W3s + bh * md + (int64_t)j0 * dh, min(G::BP / 2, m - j0), ldb,
           (unsigned)ldb);
+  DmaOp<G::NW, G::BQ> oq;
+  oq.init(X + (int64_t)r0 * dh, nullptr, min(G::BQ, nrows - r0), ldb, (unsigned)ldb);
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
-  // Each wave's 64 Q rows are 32 W1 rows (blocks 0, 1) then the same 32 W3 rows
-  // (blocks 2, 3): block jj pairs with block jj + 2.  Every output is a
-  // [token][column] tile staged in LDS and copied out as whole row pieces:
-  // A and U of the keys together (one half of the stage area each, when they
-  // fit), then Hh = silu(A) * U, formed in place of A.
-  static_assert(G::NQB == 4 && G::BM == 16 && G::GPB == 1, "two W1/W3 block pairs per wave");
-  using ST = Staged<T, G::BQ / 2>;
-  constexpr int TILE = G::BP * ST::RB;                           // bytes of one staged output
+  // Tile row r holds W1 row ((r >> 6) << 5) + (r & 31) in even 32-row blocks and
+  // the same W3 row in odd ones, so a wave's P blocks 0, 1, 4, 5 are W1 rows and
+  // block i + 2 holds the W3 rows of block i.  Every output is a [token][hidden]
+  // tile staged in LDS and copied out as whole row pieces: A and U of the keys
+  // together (one half of the stage area each, when they fit), then
+  // Hh = silu(A) * U, formed in place of A.
+  static_assert(G::NPB == 8 && G::BM == 16 && G::GPB == 1 && G::BP / G::WP == 128,
+                "two W1/W3 block pairs per 32 rows of a wave");
+  using ST = Staged<T, G::BP / 2>;
+  constexpr int TILE = G::BQ * ST::RB;                           // bytes of one staged output
   constexpr bool PAIR = 2 * TILE <= G::Smem;
-  const int jl = (wave_id() % G::WQ) * 32 + (lane_id() & 15);      // local column of block jj = 0
-  const int jn = min(G::BQ / 2, m - j0), tn = min(G::BP, nrows - r0);
+  const int jn = min(G::BP / 2, m - j0), tn = min(G::BQ, nrows - r0);
+  auto hcol = [](int i) {                                        // local hidden unit of W1 block i
+    const int r = G::acc_p(i, 0);
+    return ((r >> 6) << 5) + (r & 31);
+  };
   // half: 0 = W1 blocks (A, later Hh), 2 = W3 blocks (U); a compile-time
   // constant, so that the accumulators stay in registers
   auto put = [&](char* base, auto half) __attribute__((always_inline)) {
     const ST st{base};
 #pragma unroll
-    for (int i = 0; i < G::NPB; ++i)
+    for (int ii = 0; ii < 4; ++ii) {
+      const int i = (ii & 1) + 4 * (ii >> 1);                    // 0, 1, 4, 5
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj + decltype(half)::value][e]);
+      for (int j = 0; j < G::NQB; ++j) {
+        const f32x4& v = acc[i + decltype(half)::value][j];
+        st.put4(G::acc_q(j), hcol(i), v[0], v[1], v[2], v[3]);
+      }
+    }
   };
-  using H0 = std::integral_constant<int, 0>;
-  using H2 = std::integral_constant<int, 2>;
   auto flush = [&](char* base, T* dst) __attribute__((always_inline)) {   // dst: [C, m] block of this bh
     const ST st{base};
     st.template flush<G::NT>(tn, [&](int r, int col) -> T* {
       return col < jn ? dst + (int64_t)(r0 + r) * m + j0 + col : nullptr;
     });
   };
+  using H0 = std::integral_constant<int, 0>;
+  using H2 = std::integral_constant<int, 2>;
   if (part) {
     T* a_ = A + (int64_t)bh * C * m;
     T* u_ = U + (int64_t)bh * C * m;
@@ -155,11 +164,13 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restr
     }
   }
 #pragma unroll
-  for (int i = 0; i < G::NPB; ++i)
+  for (int ii = 0; ii < 4; ++ii) {
+    const int i = (ii & 1) + 4 * (ii >> 1);
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int j = 0; j < G::NQB; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[i][jj][e] = silu_f(acc[i][jj][e]) * acc[i][jj + 2][e];
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = silu_f(acc[i][j][e]) * acc[i + 2][j][e];
+  }
   put(smem, H0{});
   __syncthreads();
   flush(smem, Hh + ((int64_t)part * BH + bh) * C * m);
@@ -461,8 +472,8 @@ hipError_t launch_lact(const LactArgs& a, hipStream_t s) {
       sr.qc = sr.kc = c;
       sr.nq = sr.nk = C;
     }
-    const int tp1 = (int)(cdiv(sr.nq, Wide::BP) + cdiv(sr.nk, Wide::BP));
-    k_lact_fwd1<T><<<(unsigned)(tp1 * cdiv(m, Wide::BQ / 2) * BH), Wide::NT, 0, s>>>(q, kk, W1s, W3s, Hh, A, U, BH, n,
+    const int tq1 = (int)(cdiv(sr.nq, Wide::BQ) + cdiv(sr.nk, Wide::BQ));
+    k_lact_fwd1<T><<<(unsigned)(cdiv(m, Wide::BP / 2) * tq1 * BH), Wide::NT, 0, s>>>(q, kk, W1s, W3s, Hh, A, U, BH, n,
                                                                                    dh, m, C, sr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int tq2 = (int)(cdiv(sr.nq, Wide::BQ) + cdiv(sr.nk, Wide::BQ));
