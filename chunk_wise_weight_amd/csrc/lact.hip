@@ -29,7 +29,7 @@ namespace {
 
 template <typename T> constexpr int esz() { return (int)sizeof(T); }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-constexpr int kSplit = 4;              // token splits of the weight-gradient GEMMs
+constexpr int kSplit = 2;              // token splits of the weight-gradient GEMMs
 
 // Workspace layout (byte offsets), one region per buffer.
 struct LactWs {
