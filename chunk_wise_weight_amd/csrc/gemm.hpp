@@ -82,6 +82,21 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return (bid & 7) * (full >> 3) + (bid >> 3);
 }
 
+// Group-synchronous order, for grids made of consecutive groups of `per` tiles
+// that share operands within a group (a chunk's applies, a batch row's):
+// XCD x takes the x-th eighth of every group, group after group, so that all
+// XCDs work on the same group at any time and its operands stay in the
+// last-level cache, while each XCD's concurrent tiles are still neighbours in
+// the group's own order.  Used when per % 8 == 0 and an XCD's share of a group
+// is at least 16 tiles; smaller shares scatter an XCD's concurrent tiles over
+// several groups and lose more L2 reuse than they gain (the plain XCD order,
+// where each XCD sweeps its own range of groups, is then faster).
+__device__ __forceinline__ int group_sync_tile(int bid, int total, int per) {
+  if ((per & 7) != 0 || per < 128) return xcd_remap(bid, total);
+  const int px = per >> 3, i = bid >> 3;
+  return (i / px) * per + (bid & 7) * px + (i % px);
+}
+
 // Grouped raster over a TP x TQ grid: groups of G q-tiles, p fastest inside a
 // group, so a run of consecutive ids covers a compact block of tiles.
 __device__ __forceinline__ void grouped_tile(int id, int TP, int TQ, int G, int& tp, int& tq) {

@@ -459,7 +459,7 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int id = group_sync_tile(blockIdx.x, gridDim.x, per);     // all XCDs on one chunk at a time
   const int bc = id / per;
   int tp, tq;
   grouped_tile(id - bc * per, TP, TQ, 4, tp, tq);
@@ -513,7 +513,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int id = group_sync_tile(blockIdx.x, gridDim.x, per);     // all XCDs on one batch row at a time
   const int b = id / per;
   int tp, tq;
   grouped_tile(id - b * per, TP, TQ, 4, tp, tq);
