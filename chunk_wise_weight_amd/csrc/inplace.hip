@@ -388,7 +388,10 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
   const int bs = id / per;
   const int b = bs / S, sg = bs - b * S;
   int tp, tq;
-  grouped_tile(id - bs * per, TP, TQ, 4, tp, tq);
+  // every d_model tile of one d_ff tile in one group: the tiles running at the
+  // same time then read few distinct Zt rows, and each stretch of the token
+  // stream is fetched from HBM about once rather than once per round
+  grouped_tile(id - bs * per, TP, TQ, TQ, tp, tq);
   const int k = n / C_, kS = k / S;
   const int c0 = sg * kS;
   const int j0 = tp * G::BP, i0 = tq * G::BQ;
