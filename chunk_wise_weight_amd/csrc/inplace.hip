@@ -18,16 +18,20 @@ template <typename T> constexpr int esz() { return (int)sizeof(T); }
 
 // Y = CausalDepthwiseConv1D_KW(X0) (eq. (5) with the causal padding of §3):
 // Y[t, ch] = sum_j conv_w[ch, j] * X0[t - (KW-1) + j, ch], zero before the
-// sequence start.  One thread: 4 consecutive rows x one 16-byte channel chunk.
+// sequence start.  One thread: RW consecutive rows x one 16-byte channel
+// chunk, reading each of the RW + KW - 1 input rows it needs once (a sliding
+// window; RW divides n, so a thread's rows never straddle a batch row).
+constexpr int kConvRows = 8;
 template <typename T, int KW>
 __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T* __restrict__ cw, T* __restrict__ Y,
                                               int64_t rows, int n, int d) {
-  constexpr int V = Vec<T>::V;
+  constexpr int V = Vec<T>::V, RW = kConvRows, NIN = RW + KW - 1;
   const int nchunk = d / V;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= ((rows + 3) / 4) * nchunk) return;
+  if (gid >= (rows / RW) * nchunk) return;
   const int ch = (int)(gid % nchunk) * V;
-  const int64_t r0 = (gid / nchunk) * 4;
+  const int64_t r0 = (gid / nchunk) * RW;
+  const int pos0 = (int)(r0 % n);                  // position of row r0 in its sequence
   float w[V][KW];
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(cw + (int64_t)ch * KW);
@@ -44,28 +48,29 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
       for (int e = 0; e < V; ++e) w[(c * V + e) / KW][(c * V + e) % KW] = fv[e];
     }
   }
+  // input row i of the window is X0 row r0 - (KW - 1) + i; rows before the
+  // sequence start are zero
+  u32x4 in[NIN];
+  const T* base = X0 + (r0 - (KW - 1)) * d + ch;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int64_t t = r0 + r;
-    if (t >= rows) break;
-    const int pos = (int)(t % n);
+  for (int i = 0; i < NIN; ++i)
+    in[i] = (i >= KW - 1 || pos0 + i - (KW - 1) >= 0) ? *reinterpret_cast<const u32x4*>(base + (int64_t)i * d)
+                                                      : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
     float y[V];
 #pragma unroll
     for (int v = 0; v < V; ++v) y[v] = 0.f;
 #pragma unroll
     for (int j = 0; j < KW; ++j) {
-      const int back = KW - 1 - j;
-      if (pos >= back) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(X0 + (t - back) * d + ch);
-        float xf[V];
-        if constexpr (sizeof(T) == 2) unpack8(x, xf);
-        else {
+      float xf[V];
+      if constexpr (sizeof(T) == 2) unpack8(in[r + j], xf);
+      else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) xf[e] = __uint_as_float(x[e]);
-        }
-#pragma unroll
-        for (int v = 0; v < V; ++v) y[v] = fmaf(w[v][j], xf[v], y[v]);
+        for (int e = 0; e < 4; ++e) xf[e] = __uint_as_float(in[r + j][e]);
       }
+#pragma unroll
+      for (int v = 0; v < V; ++v) y[v] = fmaf(w[v][j], xf[v], y[v]);
     }
     u32x4 o;
     if constexpr (sizeof(T) == 2) {
@@ -75,7 +80,7 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = __float_as_uint(y[e]);
     }
-    *reinterpret_cast<u32x4*>(Y + t * d + ch) = o;
+    *reinterpret_cast<u32x4*>(Y + (r0 + r) * d + ch) = o;
   }
 }
 
@@ -646,7 +651,7 @@ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 template <typename T>
 hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  const int64_t threads = cdiv(rows, 4) * (d / Vec<T>::V);
+  const int64_t threads = (rows / kConvRows) * (d / Vec<T>::V);     // rows % kConvRows == 0 (n % 8 == 0)
   const dim3 g((unsigned)cdiv(threads, 256));
   switch (K) {
 #define TTT_KW(KW) case KW: k_conv<T, KW><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d); break;
