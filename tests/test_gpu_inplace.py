@@ -213,6 +213,16 @@ def test_layer_ragged_multi_tile(dtype, mode):
     check_layer(cfg, x, O, Wf)
 
 
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_layer_chunk_synchronous_tile_order(mode):
+    """d_model 2048 with chunk 4096: one chunk (for MSE, one batch row's chunk) is 8 x 16 = 128 output tiles,
+    the size from which the applies hand every chunk to all XCDs at once; two batch rows, two chunks."""
+    eta = 0.02 if mode == "dot" else 0.5
+    cfg = small_cfg("bf16", mode, B=2, n=8192, d=2048, f=256, C=4096, eta=eta)
+    x, O, Wf = run_layer(cfg)
+    check_layer(cfg, x, O, Wf)
+
+
 def test_layer_bf16_chunk_not_multiple_of_kstep():
     # chunk 40: the dot plan falls back to materialised deltas + scan
     cfg = small_cfg("bf16", "dot", B=1, n=400, d=128, f=256, C=40, eta=0.02)
