@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="inplace_bf16_128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-secondary", action="store_true", help="skip the 32K-context secondary figure")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary figures (32K context; 128K with chunk 512)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target length of the oracle sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (reference point for HBM byte counters)")
@@ -284,6 +285,16 @@ def main():
                             "value": round(c2.tokens / (ms2 * 1e-3), 1),
                             "tflops": round(c2.flops() / (ms2 * 1e-3) / 1e12, 1),
                             "frac_bf16_mfma_peak": round(c2.flops() / (ms2 * 1e-3) / 1e12 / PEAK["bf16"], 4)}
+        torch.cuda.empty_cache()
+        # the same 128K layer with chunk 512: 256 per-chunk states instead of 32
+        c3 = ti.workload("inplace_bf16_128k_c512")
+        n3 = max(3, args.steps // 4)
+        w3, p3, _ = bench_inplace_dot(c3, n3, min(args.warmup, 1))
+        ms3 = w3 / n3 * 1e3
+        out["small_chunk"] = {"workload": c3.name, "chunk": c3.chunk, "ms_per_step": round(ms3, 4),
+                              "value": round(c3.tokens / (ms3 * 1e-3), 1),
+                              "frac_bf16_mfma_peak": round(c3.flops() / (ms3 * 1e-3) / 1e12 / PEAK["bf16"], 4),
+                              "kernels_ms": {k: round(v, 4) for k, v in p3.items()}}
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
