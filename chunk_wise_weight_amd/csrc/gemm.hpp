@@ -2,12 +2,17 @@
 //
 // A workgroup of NW = WP x WQ waves owns a BP x BQ tile acc[p][q] =
 // sum_k P[p][k] * Q[q][k] and walks K in steps of 128 bytes (64 bf16 or 32
-// fp32).  Both operands are K-contiguous in global memory.  Wave (wp, wq)
-// owns NPB x NQB 16x16 MFMA accumulator blocks (BP = 16 NPB WP,
-// BQ = 16 NQB WQ).  Every kernel uses one shape:
+// fp32).  An operand is K-contiguous in global memory (DmaOp) or MN-major,
+// one k index per row (DmaOpMN, transposed in LDS).  Wave (wp, wq) owns
+// NPB x NQB 16x16 MFMA accumulator blocks (BP = 16 NPB WP, BQ = 16 NQB WQ).
+// Every kernel uses one shape:
 //   Wide = 8 waves, 2 x 4, 8 x 4 blocks: 256 x 256 tile, 128 accumulators per
 //          lane, two waves per SIMD so that one wave's LDS and barrier waits
 //          are covered by the other's MFMAs.
+//
+// Per 64-element K step the eight waves read 192 KB of fragments from LDS and
+// the DMA writes 64 KB into it, about as many LDS cycles as the step's MFMAs
+// take: LDS bandwidth and the MFMA pipe bound the loop together.
 //
 // Global -> LDS: buffer_load_dwordx4 ... lds (LDS DMA).  One instruction moves
 // 64 lanes x 16 B = 8 rows x 128 B of a tile with no VGPR staging.  Out-of-range
