@@ -509,14 +509,16 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
 
 // ------------------------------------------------------------------ MSE objective
 
-// Apply of chunk c with the current state and the residual of its squared error:
-// O_c = Z_c W^T, Rt[b] = (O_c - V^_c)^T [B, d, C].  P = d_model rows of W
-// (W_down0 for c == 0, else this row's state copy), Q = the chunk's tokens, read
-// from Zt [B, f, n] as an MN-major operand, K = d_ff.
+// Apply of chunk c with the current state and the residual of its squared error,
+// scaled by the step: O_c = Z_c W^T, Rt[b] = rscale (O_c - V^_c)^T [B, d, C]
+// with rscale = -eta / C, so that the update is a plain accumulation
+// W + Rt Z_c.  P = d_model rows of W (W_down0 for c == 0, else this row's state
+// copy), Q = the chunk's tokens, read from Zt [B, f, n] as an MN-major operand,
+// K = d_ff.
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __restrict__ W, int64_t wsb,
                                        T* __restrict__ O, const T* __restrict__ Vt, T* __restrict__ Rt, int n, int d,
-                                       int f, int C_, int c) {
+                                       int f, int C_, int c, float rscale) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
@@ -561,7 +563,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
       __syncthreads();
     }
   }
-  // Rt [b, channel, token] = O - V^ in fp32: the accumulators are staged as
+  // Rt [b, channel, token] = rscale (O - V^) in fp32: the accumulators are staged as
   // fp32 [channel][token] rows (in passes over channels); each thread then
   // takes 8 consecutive tokens of one channel, reads V^ from Vt in one or two
   // 16-byte pieces, subtracts and writes the same span of Rt.
@@ -593,8 +595,10 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
         const f32x4 o1 = *reinterpret_cast<const f32x4*>(smem + st.off(r, t + 4));
         const f32x4 v0 = load4(vt + ch * n + t), v1 = load4(vt + ch * n + t + 4);
         T* dst = rt + ch * C_ + t;
-        store4(dst, o0[0] - v0[0], o0[1] - v0[1], o0[2] - v0[2], o0[3] - v0[3]);
-        store4(dst + 4, o1[0] - v1[0], o1[1] - v1[1], o1[2] - v1[2], o1[3] - v1[3]);
+        store4(dst, rscale * (o0[0] - v0[0]), rscale * (o0[1] - v0[1]), rscale * (o0[2] - v0[2]),
+               rscale * (o0[3] - v0[3]));
+        store4(dst + 4, rscale * (o1[0] - v1[0]), rscale * (o1[1] - v1[1]), rscale * (o1[2] - v1[2]),
+               rscale * (o1[3] - v1[3]));
       }
       __syncthreads();
     }
@@ -602,13 +606,16 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
 }
 
 // W_{c+1} = W_c - (eta / C) R_c^T Z_c (eq. (4) with the squared error at the
-// pre-update state).  P = d_ff rows of Zt (the chunk's tokens), Q = d_model rows
-// of Rt, K = C.  The fp32 state lives in Ws [B, d, f] (W_down0 before chunk 0);
-// Wsh (may be null) receives a dtype copy for the next apply.
+// pre-update state), as W_c + Rt Z_c with Rt already scaled by -eta / C.
+// P = d_ff rows of Zt (the chunk's tokens), Q = d_model rows of Rt, K = C.
+// The accumulator starts at the state -- W_down0 for c == 0, else the fp32
+// state Ws [B, d, f] -- read before the K loop, while its first operands are
+// in flight; the result goes out through LDS as whole rows: the fp32 state,
+// and into Wsh (may be null) a dtype copy for the next apply.
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __restrict__ Rt, const T* __restrict__ W0,
                                         float* __restrict__ Ws, T* __restrict__ Wsh, int n, int d, int f, int C_,
-                                        int c, float scale) {
+                                        int c) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (f + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
@@ -625,21 +632,18 @@ TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __res
   op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C_, nullptr, min(G::BP, f - j0), (uint64_t)n * esz<T>(),
           kbytes);
   oq.init(Rt + ((int64_t)b * d + i0) * C_, nullptr, min(G::BQ, d - i0), (uint64_t)kbytes, kbytes);
+  float* ws = Ws + (int64_t)b * d * f;
   typename G::Frag acc[G::NPB][G::NQB];
-  zero_acc<G>(acc);
+  zero_acc<G>(acc);                       // entries outside the state stay zero (never stored)
+  for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+    const f32x4 w = (c == 0) ? load4(W0 + ro + dj) : load4(ws + ro + dj);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
+  });
   mainloop<T, G>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
 
-  float* ws = Ws + (int64_t)b * d * f;
-  T* wsh = Wsh ? Wsh + (int64_t)b * d * f : nullptr;
-  for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
-    const int64_t o = ro + dj;
-    const f32x4 w = (c == 0) ? load4(W0 + o) : load4(ws + o);
-    float nw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) nw[e] = fmaf(-scale, acc[ib][jb][4 * g + e], w[e]);
-    store4(ws + o, nw[0], nw[1], nw[2], nw[3]);
-    if (wsh) store4(wsh + o, nw[0], nw[1], nw[2], nw[3]);
-  });
+  stage_state<G, G::Smem>(acc, ws, smem, j0, i0, d, f);
+  if (Wsh != nullptr) stage_state<G, G::Smem>(acc, Wsh + (int64_t)b * d * f, smem, j0, i0, d, f);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -730,11 +734,11 @@ hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur
   // the state chunk c is applied with: W_down0 (shared) for c == 0, else this row's copy
   const T* W = (c == 0) ? W0 : Wcur;
   const int64_t wsb = (c == 0) ? 0 : df;
-  k_mse_apply<T><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, W, wsb, O, Vt, Rt, n, d, f, Cs, c);
+  k_mse_apply<T><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, W, wsb, O, Vt, Rt, n, d, f, Cs, c,
+                                                                              -eta / (float)Cs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, n, d, f, Cs, c,
-                                                                               eta / (float)Cs);
+  k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, n, d, f, Cs, c);
   return hipGetLastError();
 }
 
