@@ -364,25 +364,21 @@ __device__ __forceinline__ void zero_acc(Acc& acc) {
 // barrier, in every wave.  It may use the stage step ks was read from
 // (C::Stage bytes at free_stage) -- the next write to it is the DMA issued at
 // the start of step ks + 2 -- provided it ends with a barrier; other LDS is
-// off limits.  Step ks uses stage (ks + s0) & 1; with issued0 the caller has
-// already issued step 0 into stage s0 (so that it lands while the caller
-// finishes other work).
+// off limits.
 template <typename T, class C, class OP, class OQ, class Hook, class Acc>
 __device__ __forceinline__ void mainloop(const OP& op, const OQ& oq, int nks, Acc& acc, char* smem,
-                                         const Hook& hook, int s0 = 0, bool issued0 = false) {
+                                         const Hook& hook) {
   // The host compilation pass only needs the kernels' signatures; instantiating
   // this body there (target builtins, inline asm) trips template deduction.
 #if defined(__HIP_DEVICE_COMPILE__)
   if (nks <= 0) return;
-  if (!issued0) {
-    op.issue(0, smem + s0 * C::Stage);
-    oq.issue(0, smem + s0 * C::Stage + C::PBytes);
-  }
+  op.issue(0, smem);
+  oq.issue(0, smem + C::PBytes);
   wait_dma();
   __syncthreads();
   for (int ks = 0; ks < nks; ++ks) {
-    char* cur = smem + ((ks + s0) & 1) * C::Stage;
-    char* nxt = smem + (((ks + s0) & 1) ^ 1) * C::Stage;
+    char* cur = smem + (ks & 1) * C::Stage;
+    char* nxt = smem + ((ks & 1) ^ 1) * C::Stage;
     if (ks + 1 < nks) {
       op.issue(ks + 1, nxt);
       oq.issue(ks + 1, nxt + C::PBytes);
