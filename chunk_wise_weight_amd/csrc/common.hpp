@@ -57,6 +57,11 @@ __device__ __forceinline__ f32x4 load4(const bf16* p) {
                  __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
 }
 __device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+// The same as a non-temporal (streaming) load: for data read once, so that it
+// does not displace what the caches hold for the other waves.
+__device__ __forceinline__ f32x4 load4_stream(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
 
 // Widen one 16-byte chunk of bf16 to 8 floats / of fp32 to 4 floats.
 __device__ __forceinline__ void unpack8(u32x4 w, float* o) {

@@ -420,12 +420,16 @@ struct Staged {
   }
   // Rows [0, nrows) out to global memory; dst(r, col) is the address of element
   // col of row r (col a multiple of EPP, 16-byte aligned) or nullptr to skip.
-  template <int NT, class Dst>
+  // STREAM: non-temporal stores, for data that is not read again soon.
+  template <int NT, class Dst, bool STREAM = false>
   __device__ __forceinline__ void flush(int nrows, Dst&& dst) const {
     for (int idx = threadIdx.x; idx < nrows * PPR; idx += NT) {
       const int r = idx / PPR, c = idx - r * PPR;
       TO* p = dst(r, c * EPP);
-      if (p != nullptr) *reinterpret_cast<u32x4*>(p) = *reinterpret_cast<const u32x4*>(base + r * RB + ((c ^ (r & 15)) << 4));
+      if (p == nullptr) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(base + r * RB + ((c ^ (r & 15)) << 4));
+      if constexpr (STREAM) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+      else *reinterpret_cast<u32x4*>(p) = v;
     }
   }
   // Transposed copy-out: output row c (c < ncols) is column c of the staged

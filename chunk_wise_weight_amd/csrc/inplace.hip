@@ -270,9 +270,9 @@ __device__ __forceinline__ void store_state(const Acc& acc, TO* __restrict__ out
 
 // store_state through LDS: the [d_model x d_ff] state tile (rows i = Q, columns
 // j = P) is staged in BUFB bytes at buf, in as many passes over its rows as
-// needed, and written out as whole 16-byte pieces along rows.  Every wave must
-// call it; it ends with a barrier.
-template <class G, int BUFB, typename TO, class Acc>
+// needed, and written out as whole 16-byte pieces along rows (non-temporal
+// stores with STREAM).  Every wave must call it; it ends with a barrier.
+template <class G, int BUFB, typename TO, class Acc, bool STREAM = false>
 __device__ __forceinline__ void stage_state(const Acc& acc, TO* __restrict__ out, char* buf, int j0, int i0, int d,
                                             int f) {
   static_assert(G::GPB == 1, "one accumulator group per block");
@@ -291,9 +291,10 @@ __device__ __forceinline__ void stage_state(const Acc& acc, TO* __restrict__ out
         st.put4(q, G::acc_p(ib, 0), acc[ib][jb][0], acc[ib][jb][1], acc[ib][jb][2], acc[ib][jb][3]);
     }
     __syncthreads();
-    st.template flush<G::NT>(max(0, min(RPP, in_ - ps * RPP)), [&](int r, int col) -> TO* {
+    auto dst = [&](int r, int col) -> TO* {
       return col < jn ? out + (int64_t)(i0 + ps * RPP + r) * f + j0 + col : nullptr;
-    });
+    };
+    st.template flush<G::NT, decltype(dst)&, STREAM>(max(0, min(RPP, in_ - ps * RPP)), dst);
     __syncthreads();
   }
 }
@@ -611,7 +612,10 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
 // The accumulator starts at the state -- W_down0 for c == 0, else the fp32
 // state Ws [B, d, f] -- read before the K loop, while its first operands are
 // in flight; the result goes out through LDS as whole rows: the fp32 state,
-// and into Wsh (may be null) a dtype copy for the next apply.
+// and into Wsh (may be null) a dtype copy for the next apply.  The fp32 state
+// is read and written with non-temporal accesses: it is next used by the
+// following chunk's update, and at long-context sizes it is larger than the
+// caches, which are better kept for the operands and for Wsh (read next).
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __restrict__ Rt, const T* __restrict__ W0,
                                         float* __restrict__ Ws, T* __restrict__ Wsh, int n, int d, int f, int C_,
@@ -636,14 +640,15 @@ TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __res
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);                       // entries outside the state stay zero (never stored)
   for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
-    const f32x4 w = (c == 0) ? load4(W0 + ro + dj) : load4(ws + ro + dj);
+    const f32x4 w = (c == 0) ? load4(W0 + ro + dj) : load4_stream(ws + ro + dj);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
   });
   mainloop<T, G>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
 
-  stage_state<G, G::Smem>(acc, ws, smem, j0, i0, d, f);
-  if (Wsh != nullptr) stage_state<G, G::Smem>(acc, Wsh + (int64_t)b * d * f, smem, j0, i0, d, f);
+  stage_state<G, G::Smem, float, decltype(acc), true>(acc, ws, smem, j0, i0, d, f);
+  if (Wsh != nullptr)
+    stage_state<G, G::Smem, T, decltype(acc), false>(acc, Wsh + (int64_t)b * d * f, smem, j0, i0, d, f);
 }
 
 // ------------------------------------------------------------------ launchers

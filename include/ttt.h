@@ -210,7 +210,13 @@ int ttt_lact_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* byt
  *   O         [B, H, n, dh]   dtype   (written)
  *   W1_f, W3_f [B, H, m, dh]  fp32    final states (written)
  *   W2_f      [B, H, dh, m]   fp32
- * Supported: head_dim, hidden, chunk multiples of 8; seq_len % chunk == 0. */
+ * Supported: head_dim, hidden, chunk multiples of 8; seq_len % chunk == 0.
+ * Streams: with two or more (batch, head) rows, half of the rows run on a side
+ * stream of the stream's device that the library creates on first use and
+ * keeps; the side work starts after everything enqueued on `stream` before
+ * the call and everything enqueued on `stream` after the call waits for it
+ * (event fork and join), so the call is ordered on `stream` like one kernel.
+ * Calls from several host threads on one device enqueue one at a time. */
 int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta,
                     const void* q, const void* k, const void* v,
                     const void* W1, const void* W3, const void* W2,

@@ -80,6 +80,29 @@ def test_lact_eta_zero_is_plain_swiglu():
     assert np.array_equal(f64(W2f[0]), ti.to_f64(x["W2"]))
 
 
+@pytest.mark.parametrize("B,H", [(1, 3), (3, 1), (2, 2)])
+def test_lact_rows_equal_single_row_calls(B, H):
+    """Every (batch, head) row is an independent fast weight.  A call on B x H rows (split into groups whose
+    chains run on separate streams, unevenly for 3 rows) gives each row bit for bit what a call on that row alone
+    gives, and a repeated call gives the same bits."""
+    cfg = cfg_small("bf16", B=B, H=H, n=384, dh=64, m=128, C=128, eta=0.7, seed=11)
+    x = ti.lact_inputs(cfg)
+    g = {k: v.cuda() for k, v in x.items()}
+    call = lambda q, k, v, W1, W3, W2: cw.ttt_lact_swiglu(q, k, v, W1, W3, W2, cfg.chunk, cfg.eta, cfg.order)
+    full = call(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"])
+    again = call(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"])
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(full, again))
+    for b in range(B):
+        for h in range(H):
+            row = lambda t: t[b:b + 1, h:h + 1].contiguous()
+            head = lambda t: t[h:h + 1].contiguous()
+            one = call(row(g["q"]), row(g["k"]), row(g["v"]), head(g["W1"]), head(g["W3"]), head(g["W2"]))
+            torch.cuda.synchronize()
+            for got, want in zip(one, full):
+                assert torch.equal(got[0, 0], want[b, h]), (b, h)
+
+
 def test_lact_single_chunk_full_batch_step():
     cfg = cfg_small("f32", n=256, C=256)
     check(cfg, *run(cfg))
