@@ -364,6 +364,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW
 // (chunks after its first) and its total to Tot[b, s - 1] -- except the last
 // segment, whose total goes to W_final.  k_scan_fixup then adds the earlier
 // segments' totals.  With S = 1 the kernel alone produces every output.
+// The states are written with non-temporal stores: the apply reads them back
+// long after the caches would have dropped them.
 template <typename T>
 struct SnapshotHook {
   T* Wc;              // [k, d, f] states of this batch row (segment 0)
@@ -377,7 +379,7 @@ struct SnapshotHook {
     if (c >= c1) return;
     const int64_t df = (int64_t)d * f;
     T* dst = c0 == 0 ? Wc + (int64_t)c * df : Wp + (int64_t)(c - kS) * df;
-    stage_state<Wide, Wide::Stage>(acc, dst, free_stage, j0, i0, d, f);
+    stage_state<Wide, Wide::Stage, T, A, true>(acc, dst, free_stage, j0, i0, d, f);
   }
 };
 
