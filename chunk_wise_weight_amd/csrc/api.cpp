@@ -63,7 +63,7 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   p->fused = mode == TTT_MODE_DOT && p->C % kstep(dtype) == 0;
   const size_t BN = (size_t)p->B * p->n, DF = (size_t)p->d * p->f;
   size_t off = 0;
-  p->S = p->fused ? ttt::update_scan_segments(p->d, p->f, p->k) : 1;
+  p->S = p->fused ? ttt::update_scan_segments(p->d, p->f, p->k, p->C) : 1;
   p->off_Y = p->off_WtT = p->off_Zt = p->off_Vt = p->off_Wc = p->off_dW = p->off_Wp = p->off_Tot = 0;
   p->off_Rt = p->off_Wsh = 0;
   if (producers) {
@@ -364,7 +364,7 @@ int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const v
 
 static size_t update_scan_ws(const ttt_inplace_shape* s, int dtype) {
   const int64_t k = s->seq_len / s->chunk;
-  const int S = ttt::update_scan_segments(s->d_model, s->d_ff, k);
+  const int S = ttt::update_scan_segments(s->d_model, s->d_ff, k, s->chunk);
   if (S == 1) return 0;
   const size_t DF = (size_t)s->d_model * s->d_ff;
   const size_t esz = dtype == TTT_BF16 ? 2 : 4;
@@ -400,7 +400,7 @@ int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void*
   if (!ok_ptr(Zt) || !ok_ptr(Vt) || !ok_ptr(Wc)) return TTT_ERR_ARG;
   const size_t need = update_scan_ws(shape, dtype);
   if (workspace_bytes < need || (need > 0 && !ok_ptr(workspace))) return TTT_ERR_WORKSPACE;
-  const int k = n / C, S = ttt::update_scan_segments(d, f, k);
+  const int k = n / C, S = ttt::update_scan_segments(d, f, k, C);
   char* ws = (char*)workspace;
   const size_t esz = dtype == TTT_BF16 ? 2 : 4;
   void* Wp = S > 1 ? (void*)ws : nullptr;

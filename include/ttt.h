@@ -175,7 +175,9 @@ int ttt_update_scan_workspace_bytes(const ttt_inplace_shape* shape, int dtype, s
  * whose fp32 accumulator starts at W_down0 and holds W_c after the tokens of
  * chunks 0..c-1; at each chunk boundary the tile writes Wc[b, c], after the
  * last chunk W_final.  When the state has too few tiles to fill the GPU, the
- * sequence runs as S side-by-side segments and a short elementwise pass adds
+ * sequence may run as S side-by-side segments (S in {1, 2, 4} dividing the
+ * chunk count, chosen from d_model, d_ff, chunk and the chunk count alone by
+ * weighing the rounds of tiles against the pass below), and a short elementwise pass adds
  * the earlier segments' totals (fp32) to the later segments' partial states
  * (kept in dtype; with bf16 a state of a later segment is thus rounded twice);
  * `workspace` (device, at least ttt_update_scan_workspace_bytes) holds the

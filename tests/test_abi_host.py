@@ -51,9 +51,12 @@ def test_workspace_sizes():
     core = lambda e, B=B: al(B * n * f * e) + al(B * n * d * e)          # Zt, Vt
     # producers: conv output and W_target^T (Z itself is only kept token-contiguous, as Zt)
     prod = lambda e: al(B * n * d * e) + al(d * d * e)
+    # the fused dot plan of this 2-tile state runs 4 sequence segments: partial states of the last 6
+    # chunks (dtype) and 3 fp32 segment totals
+    seg = lambda e: al(B * (k - k // 4) * d * f * e) + al(B * 3 * d * f * 4)
     st, nb = _ws(_shape(), cw.TTT_F32, cw.TTT_MODE_DOT, 1)
     assert st == cw.TTT_OK
-    assert nb == prod(4) + core(4) + al(B * k * d * f * 4)
+    assert nb == prod(4) + core(4) + al(B * k * d * f * 4) + seg(4)
     st, nb = _ws(_shape(), cw.TTT_BF16, cw.TTT_MODE_MSE, 1)
     assert st == cw.TTT_OK and nb == prod(2) + core(2) + al(C * d * 2) + al(d * f * 2)
     st, nb = _ws(_shape(), cw.TTT_BF16, cw.TTT_MODE_DOT_SCAN, 0)
@@ -78,24 +81,26 @@ def _update_scan_ws(shape, dtype=cw.TTT_BF16):
 
 
 def test_update_scan_segments_and_workspace():
-    """The fused update-scan runs the sequence as S segments when that fills the 256 compute units
-    markedly better for one batch row (S depends on the state's shape only, so rows do not depend on
-    the batch they are in); its scratch holds the fp32 partial states of chunks past the first
-    segment (bf16 here) and the S - 1 fp32 segment totals."""
+    """The fused update-scan runs the sequence as S segments (S in 1, 2, 4 dividing the chunk count) when
+    the model of its time -- rounds of 256 tiles times tokens per segment, plus the fix-up pass over the
+    later segments' partial states -- says so (S depends on the state's and the sequence's shape only, so
+    rows do not depend on the batch they are in); its scratch holds the partial states of chunks past the
+    first segment (bf16 here) and the S - 1 fp32 segment totals."""
     al = lambda x: (x + 255) // 256 * 256
 
     def expect(B, n, d, f, C):
         k = n // C
         tiles = -(-f // 256) * -(-d // 256)
-        fill = lambda t: t / (256 * -(-t // 256))
+        cost = lambda S: -(-tiles * S // 256) * (k * C // S) * 28.1e-9 + (k - k // S) * d * f * 4.0 / 5.5e12
         S = 1
         for cand in (2, 4):
-            if k % cand == 0 and fill(tiles * cand) > fill(tiles * S) + 0.05:
+            if k % cand == 0 and cost(cand) < cost(S):
                 S = cand
         return S, (0 if S == 1 else al(B * (k - k // S) * d * f * 2) + al(B * (S - 1) * d * f * 4))
 
     cases = [(1, 131072, 2560, 9728, 4096, 2), (1, 32768, 2560, 9728, 1024, 2), (1, 2048, 1024, 4096, 256, 4),
-             (2, 1024, 1024, 4096, 128, 4), (1, 2048, 256, 512, 256, 1), (4, 65536, 2048, 8192, 2048, 1),
+             (2, 1024, 1024, 4096, 128, 4), (1, 2048, 256, 512, 256, 4), (4, 65536, 2048, 8192, 2048, 1),
+             (1, 131072, 2560, 9728, 512, 1),    # 256 short chunks: the fix-up would cost more than it saves
              (1, 4096, 2560, 9728, 4096, 1)]     # one chunk: nothing to split
     for B, n, d, f, C, S in cases:
         s_exp, ws = expect(B, n, d, f, C)
