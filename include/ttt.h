@@ -22,13 +22,18 @@
  * Conventions common to every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller (e.g.
  *     torch.Tensor.data_ptr()), row-major and contiguous, 16-byte aligned.
- *     The library allocates nothing; scratch comes from the caller's
- *     workspace, whose size the matching *_workspace_bytes call returns.
+ *     The library allocates no device memory; scratch comes from the
+ *     caller's workspace, whose size the matching *_workspace_bytes call
+ *     returns.  (ttt_lact_swiglu creates one side stream and its events per
+ *     device on first use and keeps them.)
  *   - Inputs are read only.  Outputs and workspace must not alias inputs or
  *     each other.  W_down0 is never written: "in place" names the reuse of
  *     the MLP's own weight as the fast weight, not memory aliasing.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
- *     the default stream).  The call returns once the work is enqueued.
+ *     the default stream).  The call returns once the work is enqueued.  It
+ *     enqueues kernels only (no copy or memset; ttt_lact_swiglu adds an event
+ *     fork and join), so a call can be captured into a HIP graph and replayed
+ *     with the same buffers.
  *   - Every argument is validated before any device work is enqueued; on an
  *     error status nothing has been enqueued and outputs are untouched.  A
  *     launch failure reported by the runtime returns TTT_ERR_DEVICE, in which

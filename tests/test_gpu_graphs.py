@@ -1,0 +1,56 @@
+"""The layer calls captured into HIP graphs (torch.cuda.CUDAGraph drives the capture).
+
+The library enqueues kernels only -- no allocation, copy or memset -- and the LaCT call adds an event fork and
+join with a side stream, which a capture records as parallel branches.  Each graph is replayed three times with
+the outputs clobbered, eager calls and synchronisations in between, and every replay must reproduce the eager
+call's bits.
+"""
+import pytest
+import torch
+
+import chunk_wise_weight_amd as cw
+import ttt_inputs as ti
+
+pytestmark = pytest.mark.gpu
+
+
+def _inplace(mode):
+    cfg = ti.InplaceConfig("graph", 2, 1024, 264, 392, 256, 0.05 if mode == "dot" else 0.5, mode, "bf16", conv_k=4,
+                           seed=13)
+    g = {k: v.cuda() for k, v in ti.inplace_inputs(cfg).items()}
+    args = (g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"], g["conv_w"], cfg.chunk, cfg.eta,
+            mode)
+    return lambda: cw.ttt_chunk_apply_update(*args)
+
+
+def _lact():
+    cfg = ti.LactConfig("graph", 1, 3, 512, 64, 128, 128, 0.7, "update_then_apply", "bf16", seed=17)
+    g = {k: v.cuda() for k, v in ti.lact_inputs(cfg).items()}
+    args = (g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta, cfg.order)
+    return lambda: cw.ttt_lact_swiglu(*args)
+
+
+@pytest.mark.parametrize("kind", ["dot", "mse", "lact"])
+def test_graph_replays_match_eager(kind):
+    call = _lact() if kind == "lact" else _inplace(kind)
+    eager = call()
+    torch.cuda.synchronize()
+    # warm-up on a side stream, as torch asks before a capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = call()
+    for r in range(3):
+        for t in out:
+            t.fill_(float("nan"))
+        again = call()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(again, eager)), r
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(out, eager)), r
