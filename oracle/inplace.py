@@ -32,7 +32,12 @@ design notes of the repository):
   * mse objective: L = (1/(2C)) ||Z_c W^T - V^_c||_F^2 at the pre-update W,
     so the step is W - (eta/C)(Z_c W^T - V^_c)^T Z_c, with C the number of
     tokens in that chunk.
-  * each batch row is one document with its own state starting at W_down0.
+  * each batch row is one document with its own state starting at W_down0,
+    unless document starts are given (a packed row): a document may then
+    start at any chunk boundary, where the state is reset to W_down0 and the
+    convolution restarts (left zero padding at the document's first token),
+    so that nothing of the previous document reaches it (Method §3, document
+    boundaries).
 """
 from __future__ import annotations
 
@@ -160,13 +165,18 @@ def chunk_prefix_form(Z, Vhat, W0, chunk, eta):
 
 
 def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
-                  mode, max_chunks=None, x0_halo=None):
+                  mode, max_chunks=None, x0_halo=None, doc_starts=None):
     """The whole In-Place TTT layer, one document per batch row.
 
     H, X0 [B, n, d]; W_gate, W_up [f, d]; W_down0 [d, f]; W_target [d, d];
     conv_w [d, K].  Streams chunk by chunk: Z_c and V^_c are formed for the
     chunk only (the convolution reads the K-1 previous rows of X0, or
     `x0_halo` [B, K-1, d] before the first row, else zeros).
+
+    `doc_starts` [B, n_chunks] (truthy entries) packs several documents into a
+    row: a document starts at every flagged chunk c > 0 (chunk 0 always starts
+    one), where the state is reset to W_down0 and the convolution restarts
+    with zeros before the chunk's first row (Method §3, document boundaries).
 
     `max_chunks` stops after that many chunks (O then covers only those rows
     and W_final is the state after them) -- used to time a bounded sample.
@@ -191,9 +201,13 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
         else:
             Xfull, off = X0[b], 0
         W = _f64(W_down0).copy()       # document boundary: reset to the pretrained state
+        doc_row = 0                    # first row of the current document in Xfull (the halo serves the first)
         for c in range(n_chunks):
             s, e = c * chunk, min((c + 1) * chunk, n)
-            lo = max(0, s + off - (K - 1))
+            if c > 0 and doc_starts is not None and doc_starts[b][c]:
+                W = _f64(W_down0).copy()   # a packed document starts here
+                doc_row = s + off
+            lo = max(doc_row, s + off - (K - 1))
             Y = causal_depthwise_conv1d(Xfull[lo: e + off], conv_w)[-(e - s):]
             Vc = Y @ W_target
             Zc = gated_intermediate(H[b, s:e], W_gate, W_up)

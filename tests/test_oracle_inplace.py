@@ -335,6 +335,55 @@ def test_resume_at_chunk_boundary_with_conv_halo(mode):
     np.testing.assert_allclose(W2, Wf, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_packed_documents_equal_separate_runs(mode):
+    """Documents packed into one row (Method §3: the fast weight resets at document boundaries, and
+    nothing of one document reaches the next) give exactly what separate rows give: outputs of each
+    document, and the last document's final state."""
+    rng = _rng(25)
+    C, d, f, K = 4, 3, 5, 4
+    docs = [3, 1, 2]                                    # chunks per document
+    n = C * sum(docs)
+    H, X0, Wg, Wu, W0, Wt, cw = _problem(rng, n, d, f, K)
+    starts = np.zeros((1, n // C), dtype=bool)
+    starts[0, np.cumsum([0] + docs[:-1])] = True
+    O, Wf = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, C, 0.1, mode, doc_starts=starts)
+    row = 0
+    for nc in docs:
+        r = slice(row, row + nc * C)
+        Od, Wd = orc.inplace_layer(H[None, r], X0[None, r], Wg, Wu, W0, Wt, cw, C, 0.1, mode)
+        np.testing.assert_allclose(O[0, r], Od[0], rtol=1e-12, atol=1e-12)
+        row += nc * C
+    np.testing.assert_allclose(Wf, Wd, rtol=1e-12, atol=1e-12)
+    # flags only at chunk 0 (or none) are the single-document row
+    first = np.zeros_like(starts)
+    first[0, 0] = True
+    O1, W1 = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, C, 0.1, mode, doc_starts=first)
+    O2, W2 = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, C, 0.1, mode)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(W1, W2)
+
+
+def test_document_at_every_chunk_is_the_plain_mlp():
+    """A document starting at every chunk: each chunk sees W_down0 (the plain gated MLP of eq. (1)), and the
+    final state is one dot step on the last chunk alone, with its convolution zero-padded at its own start."""
+    rng = _rng(26)
+    n, C, d, f, K = 12, 4, 3, 5, 3
+    H, X0, Wg, Wu, W0, Wt, cw = _problem(rng, n, d, f, K)
+    starts = np.ones((1, n // C), dtype=bool)
+    O, Wf = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, C, 0.3, "dot", doc_starts=starts)
+    Zfull = F.silu(torch.from_numpy(H @ Wg.T)).numpy() * (H @ Wu.T)
+    np.testing.assert_allclose(O[0], Zfull @ W0.T, rtol=1e-12, atol=1e-12)
+    last = slice(n - C, n)
+    Ylast = np.zeros((C, d))                            # conv of the last chunk alone, by hand
+    for t in range(C):
+        for j in range(K):
+            src = t - (K - 1) + j
+            if src >= 0:
+                Ylast[t] += cw[:, j] * X0[n - C + src]
+    np.testing.assert_allclose(Wf[0], W0 + 0.3 * (Ylast @ Wt).T @ Zfull[last], rtol=1e-12, atol=1e-12)
+
+
 def test_layer_matches_whole_sequence_composition():
     # streaming per chunk must equal forming Z and V^ over the whole sequence first
     rng = _rng(22)
