@@ -27,6 +27,7 @@ struct Plan {
   int S;              // sequence segments of the fused update-scan
   // workspace regions (byte offsets); Y and WtT only with the producers
   size_t off_Y, off_WtT, off_Zt, off_Vt, off_Wc, off_dW, off_Wp, off_Tot, off_Rt, off_Wsh, total;
+  const uint8_t* docs;  // document starts [B, k] (device) or null: one document per batch row
 };
 
 int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
@@ -52,6 +53,7 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   int st = check_inplace_shape(s, dtype);
   if (st != TTT_OK) return st;
   if (mode != TTT_MODE_DOT && mode != TTT_MODE_MSE && mode != TTT_MODE_DOT_SCAN) return TTT_ERR_ARG;
+  p->docs = nullptr;
   p->B = s->batch;
   p->n = s->seq_len;
   p->d = s->d_model;
@@ -105,7 +107,8 @@ inline int dev(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
 // W_final[b] = W_down0 for every row (no chunks): the scan with zero chunks.
 template <typename T>
 int fill_initial_state(const Plan& p, const void* W0, float* Wf, hipStream_t s) {
-  return dev(ttt::launch_chunk_scan<T>(nullptr, (const T*)W0, nullptr, Wf, (int)p.B, 0, (int64_t)p.d * p.f, 0.f, s));
+  return dev(ttt::launch_chunk_scan<T>(nullptr, (const T*)W0, nullptr, Wf, (int)p.B, 0, (int64_t)p.d * p.f, 0.f, nullptr,
+                                       s));
 }
 
 // Scale the target is produced with: the fused dot update takes eta folded
@@ -133,7 +136,7 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
     T* Wsh = p.esz == 2 ? (T*)(ws + p.off_Wsh) : nullptr;
     const T* Wcur = p.esz == 2 ? (const T*)Wsh : (const T*)(const void*)Wf;
     for (int c = 0; c < k; ++c) {
-      int st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, B, n, d, f, C, c, eta, s));
+      int st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, p.docs, B, n, d, f, C, c, eta, s));
       if (st != TTT_OK) return st;
     }
     return TTT_OK;
@@ -142,11 +145,11 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
   int st;
   if (p.fused) {
     st = dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (T*)(ws + p.off_Wp), (float*)(ws + p.off_Tot),
-                                              B, n, d, f, C, p.S, s));   // Vt carries eta
+                                              B, n, d, f, C, p.S, p.docs, s));   // Vt carries eta
   } else {
     float* dW = (float*)(ws + p.off_dW);
     st = dev(ttt::launch_chunk_delta<T>(Zt, Vt, dW, B, n, d, f, C, s));
-    if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, df, eta, s));
+    if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, df, eta, p.docs, s));
   }
   if (st != TTT_OK) return st;
   return dev(ttt::launch_apply<T>(Zt, Wc, (int64_t)k * df, df, O, B, n, d, f, C, s));
@@ -162,7 +165,7 @@ int run_producers(const Plan& p, const void* H, const void* X0, const void* Wg, 
   T* Y = (T*)(ws + p.off_Y);
   T* WtT = (T*)(ws + p.off_WtT);
   int st = dev(ttt::launch_produce_z<T>((const T*)H, (const T*)Wg, (const T*)Wu, nullptr, Zt, rows, n, d, f, s));
-  if (st == TTT_OK) st = dev(ttt::launch_conv<T>((const T*)X0, (const T*)cw, Y, rows, n, d, (int)p.K, s));
+  if (st == TTT_OK) st = dev(ttt::launch_conv<T>((const T*)X0, (const T*)cw, Y, rows, n, d, (int)p.K, p.docs, (int)p.C, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Wt, WtT, 1, d, d, 1.0f, s));
   if (st == TTT_OK) st = dev(ttt::launch_produce_vhat<T>(Y, WtT, Vt, rows, n, d, vscale, s));
   return st;
@@ -247,6 +250,30 @@ int ttt_chunk_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, 
   return layer<float>(p, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, ws, s);
 }
 
+int ttt_chunk_apply_update_docs(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* H,
+                                const void* X0, const void* W_gate, const void* W_up, const void* W_down0,
+                                const void* W_target, const void* conv_w, const unsigned char* doc_starts, void* O,
+                                float* W_final, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, dtype, mode, true, &p);
+  if (st != TTT_OK) return st;
+  if (!finite(eta)) return TTT_ERR_ARG;
+  if (p.B > 0) {
+    if (!ok_ptr(W_down0) || !ok_ptr(W_final)) return TTT_ERR_ARG;
+    if (p.n > 0 && (!ok_ptr(H) || !ok_ptr(X0) || !ok_ptr(W_gate) || !ok_ptr(W_up) || !ok_ptr(W_target) ||
+                    !ok_ptr(conv_w) || !ok_ptr(O)))
+      return TTT_ERR_ARG;
+  }
+  if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
+  p.docs = doc_starts;
+  if (p.docs != nullptr) p.S = 1;     // resets are absolute: the update-scan runs as one segment
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (dtype == TTT_BF16)
+    return layer<bf16>(p, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, ws, s);
+  return layer<float>(p, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, ws, s);
+}
+
 int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* Z,
                           const void* Vhat, const void* W_down0, void* O, float* W_final, void* workspace,
                           size_t workspace_bytes, void* stream) {
@@ -313,7 +340,8 @@ int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, float scale, con
   char* ws = (char*)workspace;
   const int n = (int)p.n, d = (int)p.d, K = (int)p.K;
   if (dtype == TTT_BF16) {
-    st = dev(ttt::launch_conv<bf16>((const bf16*)X0, (const bf16*)conv_w, (bf16*)(ws + p.off_Y), rows, n, d, K, s));
+    st = dev(ttt::launch_conv<bf16>((const bf16*)X0, (const bf16*)conv_w, (bf16*)(ws + p.off_Y), rows, n, d, K, nullptr,
+                                    (int)p.C, s));
     if (st == TTT_OK)
       st = dev(ttt::launch_transpose<bf16>((const bf16*)W_target, (bf16*)(ws + p.off_WtT), 1, d, d, 1.0f, s));
     if (st == TTT_OK)
@@ -321,7 +349,8 @@ int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, float scale, con
                                               rows, n, d, scale, s));
     return st;
   }
-  st = dev(ttt::launch_conv<float>((const float*)X0, (const float*)conv_w, (float*)(ws + p.off_Y), rows, n, d, K, s));
+  st = dev(ttt::launch_conv<float>((const float*)X0, (const float*)conv_w, (float*)(ws + p.off_Y), rows, n, d, K,
+                                   nullptr, (int)p.C, s));
   if (st == TTT_OK)
     st = dev(ttt::launch_transpose<float>((const float*)W_target, (float*)(ws + p.off_WtT), 1, d, d, 1.0f, s));
   if (st == TTT_OK)
@@ -357,9 +386,9 @@ int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const v
   const int64_t df = shape->d_model * shape->d_ff;
   if (dtype == TTT_BF16)
     return dev(ttt::launch_chunk_scan<bf16>(dW, (const bf16*)W_down0, (bf16*)Wc, W_final, (int)shape->batch, k, df,
-                                            eta, s));
+                                            eta, nullptr, s));
   return dev(ttt::launch_chunk_scan<float>(dW, (const float*)W_down0, (float*)Wc, W_final, (int)shape->batch, k, df,
-                                           eta, s));
+                                           eta, nullptr, s));
 }
 
 static size_t update_scan_ws(const ttt_inplace_shape* s, int dtype) {
@@ -394,8 +423,10 @@ int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void*
   const int64_t df = (int64_t)d * f;
   if (n == 0) {
     if (dtype == TTT_BF16)
-      return dev(ttt::launch_chunk_scan<bf16>(nullptr, (const bf16*)W_down0, nullptr, W_final, B, 0, df, 0.f, s));
-    return dev(ttt::launch_chunk_scan<float>(nullptr, (const float*)W_down0, nullptr, W_final, B, 0, df, 0.f, s));
+      return dev(ttt::launch_chunk_scan<bf16>(nullptr, (const bf16*)W_down0, nullptr, W_final, B, 0, df, 0.f, nullptr,
+                                                s));
+    return dev(ttt::launch_chunk_scan<float>(nullptr, (const float*)W_down0, nullptr, W_final, B, 0, df, 0.f,
+                                                 nullptr, s));
   }
   if (!ok_ptr(Zt) || !ok_ptr(Vt) || !ok_ptr(Wc)) return TTT_ERR_ARG;
   const size_t need = update_scan_ws(shape, dtype);
@@ -407,9 +438,10 @@ int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void*
   float* Tot = S > 1 ? (float*)(ws + align_up((size_t)B * (k - k / S) * df * esz)) : nullptr;
   if (dtype == TTT_BF16)
     return dev(ttt::launch_chunk_update_scan<bf16>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)W_down0, (bf16*)Wc,
-                                                   W_final, (bf16*)Wp, Tot, B, n, d, f, C, S, s));
+                                                   W_final, (bf16*)Wp, Tot, B, n, d, f, C, S, nullptr, s));
   return dev(ttt::launch_chunk_update_scan<float>((const float*)Zt, (const float*)Vt, (const float*)W_down0,
-                                                  (float*)Wc, W_final, (float*)Wp, Tot, B, n, d, f, C, S, s));
+                                                  (float*)Wc, W_final, (float*)Wp, Tot, B, n, d, f, C, S, nullptr,
+                                                  s));
 }
 
 int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Zt, const void* Wc, void* O, void* stream) {

@@ -12,6 +12,15 @@
 
 namespace ttt {
 
+// Packed documents: docs [B, k] (may be null) flags the chunks that start a new
+// document in their batch row; chunk 0 always starts one.  At a document start
+// the state starts again from W_down0 and the convolution from zeros, so that
+// nothing of the previous document reaches it (Method §3, document boundaries).
+__device__ __forceinline__ bool doc_start(const uint8_t* __restrict__ docs, int64_t b, int k, int c) {
+  return c == 0 || (docs != nullptr && docs[b * k + c] != 0);
+}
+
+
 template <typename T> constexpr int esz() { return (int)sizeof(T); }
 
 // ------------------------------------------------------------------ conv, transpose
@@ -24,7 +33,7 @@ template <typename T> constexpr int esz() { return (int)sizeof(T); }
 constexpr int kConvRows = 8;
 template <typename T, int KW>
 __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T* __restrict__ cw, T* __restrict__ Y,
-                                              int64_t rows, int n, int d) {
+                                              int64_t rows, int n, int d, const uint8_t* __restrict__ docs, int C_) {
   constexpr int V = Vec<T>::V, RW = kConvRows, NIN = RW + KW - 1;
   const int nchunk = d / V;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -32,6 +41,8 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
   const int ch = (int)(gid % nchunk) * V;
   const int64_t r0 = (gid / nchunk) * RW;
   const int pos0 = (int)(r0 % n);                  // position of row r0 in its sequence
+  // first row of its document: the thread's rows lie in one chunk (C_ % 8 == 0)
+  const int lo = doc_start(docs, r0 / n, n / C_, pos0 / C_) ? (pos0 / C_) * C_ : 0;
   float w[V][KW];
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(cw + (int64_t)ch * KW);
@@ -49,12 +60,12 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
     }
   }
   // input row i of the window is X0 row r0 - (KW - 1) + i; rows before the
-  // sequence start are zero
+  // document start are zero
   u32x4 in[NIN];
   const T* base = X0 + (r0 - (KW - 1)) * d + ch;
 #pragma unroll
   for (int i = 0; i < NIN; ++i)
-    in[i] = (i >= KW - 1 || pos0 + i - (KW - 1) >= 0) ? *reinterpret_cast<const u32x4*>(base + (int64_t)i * d)
+    in[i] = (i >= KW - 1 || pos0 + i - (KW - 1) >= lo) ? *reinterpret_cast<const u32x4*>(base + (int64_t)i * d)
                                                       : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
@@ -333,7 +344,7 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_delta(const T* __restrict__ Zt, const T* __re
 template <typename T>
 __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW, const T* __restrict__ W0,
                                                     T* __restrict__ Wc, float* __restrict__ Wf, int k, int64_t df,
-                                                    float eta) {
+                                                    float eta, const uint8_t* __restrict__ docs) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   const int b = blockIdx.y;
   if (e >= df) return;
@@ -342,6 +353,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW
   const float* src = dW + (int64_t)b * k * df + e;
   T* dst = Wc + (int64_t)b * k * df + e;
   for (int c = 0; c < k; ++c) {
+    if (doc_start(docs, b, k, c)) s = (f32x4){0.f, 0.f, 0.f, 0.f};
     store4(dst + (int64_t)c * df, fmaf(eta, s[0], w0[0]), fmaf(eta, s[1], w0[1]), fmaf(eta, s[2], w0[2]),
            fmaf(eta, s[3], w0[3]));
     s += load4(src + (int64_t)c * df);
@@ -370,13 +382,23 @@ template <typename T>
 struct SnapshotHook {
   T* Wc;              // [k, d, f] states of this batch row (segment 0)
   T* Wp;              // partial states of this batch row; chunk c at Wp + (c - kS) d f (later segments)
-  int steps_per_chunk, c0, c1, kS, j0, i0, d, f;
+  const T* W0;        // W_down0, the state a packed document starts from
+  const uint8_t* docs;  // document starts [B, k] or null (then S == 1 is not required)
+  int64_t b;
+  int k, steps_per_chunk, c0, c1, kS, j0, i0, d, f;
   template <class A>
   __device__ __forceinline__ void operator()(int ks, A& acc, char* free_stage) const {
     const int done = ks + 1;
     if (done % steps_per_chunk != 0) return;
     const int c = c0 + done / steps_per_chunk;
     if (c >= c1) return;
+    if (docs != nullptr && docs[b * k + c] != 0) {     // a document starts at chunk c (one segment only)
+      for_state_quads<Wide>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+        const f32x4 w = load4(W0 + ro + dj);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
+      });
+    }
     const int64_t df = (int64_t)d * f;
     T* dst = c0 == 0 ? Wc + (int64_t)c * df : Wp + (int64_t)(c - kS) * df;
     stage_state<Wide, Wide::Stage, T, A, true>(acc, dst, free_stage, j0, i0, d, f);
@@ -387,7 +409,7 @@ template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T* __restrict__ Vt,
                                                const T* __restrict__ W0, T* __restrict__ Wc, T* __restrict__ Wp,
                                                float* __restrict__ Tot, float* __restrict__ Wf, int n, int d, int f,
-                                               int C_, int S) {
+                                               int C_, int S, const uint8_t* __restrict__ docs) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (f + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
@@ -422,8 +444,8 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
     });
     stage_state<G, G::Smem>(acc, wc, smem, j0, i0, d, f);                // chunk 0: W_down0
   }
-  const SnapshotHook<T> hook{wc, Wp + (int64_t)b * (k - kS) * df, C_ * esz<T>() / 128, c0, c0 + kS, kS,
-                             j0, i0, d, f};
+  const SnapshotHook<T> hook{wc, Wp + (int64_t)b * (k - kS) * df, W0, docs, b, k, C_ * esz<T>() / 128, c0,
+                             c0 + kS, kS, j0, i0, d, f};
   mainloop<T, G>(op, oq, (int)(kbytes / 128), acc, smem, hook);
   float* out = sg == S - 1 ? Wf + (int64_t)b * df : Tot + ((int64_t)b * (S - 1) + sg) * df;
   stage_state<G, G::Smem>(acc, out, smem, j0, i0, d, f);
@@ -515,13 +537,14 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
 // Apply of chunk c with the current state and the residual of its squared error,
 // scaled by the step: O_c = Z_c W^T, Rt[b] = rscale (O_c - V^_c)^T [B, d, C]
 // with rscale = -eta / C, so that the update is a plain accumulation
-// W + Rt Z_c.  P = d_model rows of W (W_down0 for c == 0, else this row's state
+// W + Rt Z_c.  P = d_model rows of W (W_down0 where a document starts, else this row's state
 // copy), Q = the chunk's tokens, read from Zt [B, f, n] as an MN-major operand,
 // K = d_ff.
 template <typename T>
-TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __restrict__ W, int64_t wsb,
-                                       T* __restrict__ O, const T* __restrict__ Vt, T* __restrict__ Rt, int n, int d,
-                                       int f, int C_, int c, float rscale) {
+TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __restrict__ W0,
+                                       const T* __restrict__ Wcur, T* __restrict__ O, const T* __restrict__ Vt,
+                                       T* __restrict__ Rt, const uint8_t* __restrict__ docs, int n, int d, int f,
+                                       int C_, int c, float rscale) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
@@ -536,7 +559,9 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
 
   DmaOp<G::NW, G::BP> op;
   DmaOpMN<T, G::NW, G::BQ> oq;
-  op.init(W + (int64_t)b * wsb + (int64_t)i0 * f, nullptr, min(G::BP, d - i0), ldb, (unsigned)ldb);
+  // the state chunk c is applied with: W_down0 (shared) where a document starts, else this row's state copy
+  const T* W = doc_start(docs, b, n / C_, c) ? W0 : Wcur + (int64_t)b * d * f;
+  op.init(W + (int64_t)i0 * f, nullptr, min(G::BP, d - i0), ldb, (unsigned)ldb);
   oq.init(Zt + (int64_t)b * f * n + (int64_t)c * C_ + t0, min(G::BQ, C_ - t0), (uint64_t)n * esz<T>(), f);
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
@@ -611,7 +636,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
 // W_{c+1} = W_c - (eta / C) R_c^T Z_c (eq. (4) with the squared error at the
 // pre-update state), as W_c + Rt Z_c with Rt already scaled by -eta / C.
 // P = d_ff rows of Zt (the chunk's tokens), Q = d_model rows of Rt, K = C.
-// The accumulator starts at the state -- W_down0 for c == 0, else the fp32
+// The accumulator starts at the state -- W_down0 where a document starts, else the fp32
 // state Ws [B, d, f] -- read before the K loop, while its first operands are
 // in flight; the result goes out through LDS as whole rows: the fp32 state,
 // and into Wsh (may be null) a dtype copy for the next apply.  The fp32 state
@@ -620,8 +645,8 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
 // caches, which are better kept for the operands and for Wsh (read next).
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __restrict__ Rt, const T* __restrict__ W0,
-                                        float* __restrict__ Ws, T* __restrict__ Wsh, int n, int d, int f, int C_,
-                                        int c) {
+                                        float* __restrict__ Ws, T* __restrict__ Wsh, const uint8_t* __restrict__ docs,
+                                        int n, int d, int f, int C_, int c) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (f + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
@@ -641,8 +666,9 @@ TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __res
   float* ws = Ws + (int64_t)b * d * f;
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);                       // entries outside the state stay zero (never stored)
+  const bool fresh = doc_start(docs, b, n / C_, c);
   for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
-    const f32x4 w = (c == 0) ? load4(W0 + ro + dj) : load4_stream(ws + ro + dj);
+    const f32x4 w = fresh ? load4(W0 + ro + dj) : load4_stream(ws + ro + dj);
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
   });
@@ -660,12 +686,13 @@ constexpr int kWB = Wide::BP;       // 256 x 256 tiles
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <typename T>
-hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, hipStream_t s) {
+hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, const uint8_t* docs, int C,
+                       hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int64_t threads = (rows / kConvRows) * (d / Vec<T>::V);     // rows % kConvRows == 0 (n % 8 == 0)
   const dim3 g((unsigned)cdiv(threads, 256));
   switch (K) {
-#define TTT_KW(KW) case KW: k_conv<T, KW><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d); break;
+#define TTT_KW(KW) case KW: k_conv<T, KW><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d, docs, C); break;
     TTT_KW(1) TTT_KW(2) TTT_KW(3) TTT_KW(4) TTT_KW(5) TTT_KW(6) TTT_KW(7) TTT_KW(8)
 #undef TTT_KW
     default: return hipErrorInvalidValue;
@@ -706,18 +733,19 @@ hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n,
 
 template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
-                             hipStream_t s) {
+                             const uint8_t* docs, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  k_chunk_scan<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(dW, W0, Wc, Wf, k, df, eta);
+  k_chunk_scan<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(dW, W0, Wc, Wf, k, df, eta, docs);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
-                                    int B, int n, int d, int f, int Cs, int S, hipStream_t s) {
+                                    int B, int n, int d, int f, int Cs, int S, const uint8_t* docs, hipStream_t s) {
+  if (docs != nullptr && S != 1) return hipErrorInvalidValue;    // document resets run as one segment
   const int64_t tiles = cdiv(f, kWB) * cdiv(d, kWB) * B * S;
   if (tiles == 0) return hipSuccess;
-  k_chunk_update_scan<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f, Cs, S);
+  k_chunk_update_scan<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f, Cs, S, docs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t df = (int64_t)d * f;
@@ -736,34 +764,33 @@ hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O,
 
 template <typename T>
 hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
-                            T* Rt, int B, int n, int d, int f, int Cs, int c, float eta, hipStream_t s) {
-  const int64_t df = (int64_t)d * f;
-  // the state chunk c is applied with: W_down0 (shared) for c == 0, else this row's copy
-  const T* W = (c == 0) ? W0 : Wcur;
-  const int64_t wsb = (c == 0) ? 0 : df;
-  k_mse_apply<T><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, W, wsb, O, Vt, Rt, n, d, f, Cs, c,
-                                                                              -eta / (float)Cs);
+                            T* Rt, const uint8_t* docs, int B, int n, int d, int f, int Cs, int c, float eta,
+                            hipStream_t s) {
+  k_mse_apply<T><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, docs, n, d,
+                                                                              f, Cs, c, -eta / (float)Cs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, n, d, f, Cs, c);
+  k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, docs, n, d, f,
+                                                                               Cs, c);
   return hipGetLastError();
 }
 
 #define TTT_INST(T)                                                                                               \
-  template hipError_t launch_conv<T>(const T*, const T*, T*, int64_t, int, int, int, hipStream_t);                \
+  template hipError_t launch_conv<T>(const T*, const T*, T*, int64_t, int, int, int, const uint8_t*, int,        \
+                                     hipStream_t);                                                                \
   template hipError_t launch_transpose<T>(const T*, T*, int, int, int, float, hipStream_t);                      \
   template hipError_t launch_produce_z<T>(const T*, const T*, const T*, T*, T*, int64_t, int, int, int,          \
                                           hipStream_t);                                                           \
   template hipError_t launch_produce_vhat<T>(const T*, const T*, T*, int64_t, int, int, float, hipStream_t);     \
   template hipError_t launch_chunk_delta<T>(const T*, const T*, float*, int, int, int, int, int, hipStream_t);   \
   template hipError_t launch_chunk_scan<T>(const float*, const T*, T*, float*, int, int, int64_t, float,         \
-                                           hipStream_t);                                                          \
+                                           const uint8_t*, hipStream_t);                                          \
   template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, T*, float*, int,      \
-                                                  int, int, int, int, int, hipStream_t);                          \
+                                                  int, int, int, int, int, const uint8_t*, hipStream_t);          \
   template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int,          \
                                       hipStream_t);                                                               \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
-                                          int, int, int, int, int, int, float, hipStream_t);
+                                          const uint8_t*, int, int, int, int, int, int, float, hipStream_t);
 TTT_INST(float)
 TTT_INST(bf16)
 #undef TTT_INST

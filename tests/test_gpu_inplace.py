@@ -223,6 +223,34 @@ def test_layer_chunk_synchronous_tile_order(mode):
     check_layer(cfg, x, O, Wf)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["dot", "dot_scan", "mse"])
+def test_layer_packed_documents(dtype, mode):
+    """Rows packing several documents (ttt_chunk_apply_update_docs): at every flagged chunk the state restarts
+    from W_down0 and the convolution from zeros, against the oracle with the same document starts.  Row 0 packs
+    documents of 3, 1 and 2 chunks, row 1 starts one at every chunk, row 2 holds a single document."""
+    eta = 0.05 if mode != "mse" else 0.5
+    cfg = small_cfg(dtype, mode, B=3, n=1536, d=264, f=392, C=256, eta=eta)
+    k = cfg.seq_len // cfg.chunk
+    starts = np.zeros((3, k), dtype=np.uint8)
+    starts[0, [0, 3, 4]] = 1
+    starts[1, :] = 1
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    O, Wf = cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"],
+                                      g["conv_w"], cfg.chunk, cfg.eta, mode,
+                                      doc_starts=torch.from_numpy(starts).cuda())
+    torch.cuda.synchronize()
+    Oref, Wref = orc.inplace_layer(*(ti.to_f64(x[n]) for n in ("H", "X0", "W_gate", "W_up", "W_down0", "W_target",
+                                                                "conv_w")), cfg.chunk, cfg.eta,
+                                   "dot" if mode == "dot_scan" else mode, doc_starts=starts)
+    W0 = ti.to_f64(x["W_down0"])
+    tol = TOL[dtype]
+    for b in range(3):
+        assert rel(f64(O[b]), Oref[b]) < tol, b
+        assert rel(f64(Wf[b]), Wref[b]) < tol and rel(f64(Wf[b]) - W0, Wref[b] - W0) < tol, b
+
+
 def test_layer_bf16_chunk_not_multiple_of_kstep():
     # chunk 40: the dot plan falls back to materialised deltas + scan
     cfg = small_cfg("bf16", "dot", B=1, n=400, d=128, f=256, C=40, eta=0.02)
