@@ -151,8 +151,11 @@ def bench_generic(cfg, steps, warmup):
     else:
         x = ti.inplace_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
+        flags = cfg.doc_starts()
+        docs = None if flags is None else torch.from_numpy(flags).cuda()
         call = lambda: cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"],
-                                                 g["W_target"], g["conv_w"], cfg.chunk, cfg.eta, cfg.mode)
+                                                 g["W_target"], g["conv_w"], cfg.chunk, cfg.eta, cfg.mode,
+                                                 doc_starts=docs)
     for _ in range(warmup):
         call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -187,10 +190,12 @@ def cpu_baseline(cfg, target_s):
     else:
         x = ti.inplace_inputs(cfg)
         ws = {k: ti.to_f64(x[k]) for k in ("W_gate", "W_up", "W_down0", "W_target", "conv_w")}
+        flags = cfg.doc_starts()
         run = lambda kc: orc.inplace_layer(ti.to_f64(x["H"][:1, : kc * cfg.chunk]),
                                            ti.to_f64(x["X0"][:1, : kc * cfg.chunk]), ws["W_gate"], ws["W_up"],
                                            ws["W_down0"], ws["W_target"], ws["conv_w"], cfg.chunk, cfg.eta,
-                                           "dot" if cfg.mode == "dot_scan" else cfg.mode)
+                                           "dot" if cfg.mode == "dot_scan" else cfg.mode,
+                                           doc_starts=None if flags is None else flags[:1, :kc])
     t0 = time.perf_counter()
     run(1)
     t1 = time.perf_counter() - t0
@@ -250,8 +255,10 @@ def main():
         out["config"] = {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_len, "d_model": cfg.d_model,
                          "d_ff": cfg.d_ff, "chunk": cfg.chunk, "conv_k": cfg.conv_k, "eta": cfg.eta,
                          "mode": cfg.mode}
+        if cfg.docs > 1:
+            out["config"]["docs_per_row"] = cfg.docs
 
-    if not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot":
+    if not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot" and cfg.docs == 1:
         wall, per, _ = bench_inplace_dot(cfg, args.steps, args.warmup)
         fl, by = kernel_flops(cfg), kernel_bytes(cfg, 2 if dtype == "bf16" else 4)
         kern = {}

@@ -266,7 +266,6 @@ int ttt_chunk_apply_update_docs(const ttt_inplace_shape* shape, int dtype, int m
   }
   if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
   p.docs = doc_starts;
-  if (p.docs != nullptr) p.S = 1;     // resets are absolute: the update-scan runs as one segment
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if (dtype == TTT_BF16)

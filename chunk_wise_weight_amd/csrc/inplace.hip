@@ -376,6 +376,9 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW
 // (chunks after its first) and its total to Tot[b, s - 1] -- except the last
 // segment, whose total goes to W_final.  k_scan_fixup then adds the earlier
 // segments' totals.  With S = 1 the kernel alone produces every output.
+// With packed documents the accumulator is set to W_down0 at every document
+// start (a segment that begins with one starts from W_down0), so from there
+// on a segment's states are absolute and the fix-up leaves them as they are.
 // The states are written with non-temporal stores: the apply reads them back
 // long after the caches would have dropped them.
 template <typename T>
@@ -383,7 +386,7 @@ struct SnapshotHook {
   T* Wc;              // [k, d, f] states of this batch row (segment 0)
   T* Wp;              // partial states of this batch row; chunk c at Wp + (c - kS) d f (later segments)
   const T* W0;        // W_down0, the state a packed document starts from
-  const uint8_t* docs;  // document starts [B, k] or null (then S == 1 is not required)
+  const uint8_t* docs;  // document starts [B, k] or null
   int64_t b;
   int k, steps_per_chunk, c0, c1, kS, j0, i0, d, f;
   template <class A>
@@ -392,7 +395,7 @@ struct SnapshotHook {
     if (done % steps_per_chunk != 0) return;
     const int c = c0 + done / steps_per_chunk;
     if (c >= c1) return;
-    if (docs != nullptr && docs[b * k + c] != 0) {     // a document starts at chunk c (one segment only)
+    if (docs != nullptr && docs[b * k + c] != 0) {     // a document starts at chunk c: its state is absolute
       for_state_quads<Wide>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
         const f32x4 w = load4(W0 + ro + dj);
 #pragma unroll
@@ -443,6 +446,13 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
       for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
     });
     stage_state<G, G::Smem>(acc, wc, smem, j0, i0, d, f);                // chunk 0: W_down0
+  } else if (docs != nullptr && docs[(int64_t)b * k + c0] != 0) {
+    // a document starts with this segment: its states are absolute from the start (the fix-up writes chunk c0's)
+    for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+      const f32x4 w = load4(W0 + ro + dj);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
+    });
   }
   const SnapshotHook<T> hook{wc, Wp + (int64_t)b * (k - kS) * df, W0, docs, b, k, C_ * esz<T>() / 128, c0,
                              c0 + kS, kS, j0, i0, d, f};
@@ -453,30 +463,45 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
 
 // Completes a segmented update-scan: adds to every partial state of segments
 // 1..S-1, and to W_final, the total of the segments before it, rounding each
-// state once to the operand dtype.  Four elements per thread, grid.y = batch.
+// state once to the operand dtype.  With packed documents a state is absolute
+// (nothing to add) from the first document start in its segment on, a
+// segment's first chunk is W_down0 when a document starts there, and the
+// offset carried to the next segment is its absolute end state if a document
+// started within it.  Four elements per thread, grid.y = batch.
 template <typename T>
 __global__ __launch_bounds__(256) void k_scan_fixup(T* __restrict__ Wc, const T* __restrict__ Wp,
-                                                    const float* __restrict__ Tot, float* __restrict__ Wf, int k,
-                                                    int S, int64_t df) {
+                                                    const float* __restrict__ Tot, float* __restrict__ Wf,
+                                                    const T* __restrict__ W0, const uint8_t* __restrict__ docs,
+                                                    int k, int S, int64_t df) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= df) return;
   const int b = blockIdx.y, kS = k / S;
   T* wc = Wc + (int64_t)b * k * df + e;
   const T* wp = Wp + (int64_t)b * (k - kS) * df + e;
   const float* tot = Tot + (int64_t)b * (S - 1) * df + e;
-  f32x4 off = load4(tot);                                   // W_down0 + segment 0
+  f32x4 off = load4(tot);                                   // W_down0 + segment 0 (absolute)
+  bool abs_ = false;                                        // a document started in the current segment
   for (int sg = 1; sg < S; ++sg) {
     const int c0 = sg * kS;
-    store4(wc + (int64_t)c0 * df, off[0], off[1], off[2], off[3]);
+    abs_ = doc_start(docs, b, k, c0);
+    const f32x4 s0 = abs_ ? load4(W0 + e) : off;
+    store4(wc + (int64_t)c0 * df, s0[0], s0[1], s0[2], s0[3]);
     for (int c = c0 + 1; c < c0 + kS; ++c) {
+      abs_ = abs_ || doc_start(docs, b, k, c);
       const f32x4 pv = load4(wp + (int64_t)(c - kS) * df);
-      store4(wc + (int64_t)c * df, off[0] + pv[0], off[1] + pv[1], off[2] + pv[2], off[3] + pv[3]);
+      if (abs_) store4(wc + (int64_t)c * df, pv[0], pv[1], pv[2], pv[3]);
+      else store4(wc + (int64_t)c * df, off[0] + pv[0], off[1] + pv[1], off[2] + pv[2], off[3] + pv[3]);
     }
-    if (sg < S - 1) off += load4(tot + (int64_t)sg * df);
+    if (sg < S - 1) {
+      const f32x4 t = load4(tot + (int64_t)sg * df);
+      off = abs_ ? t : off + t;
+    }
   }
-  float* wf = Wf + (int64_t)b * df + e;
-  const f32x4 w = load4(wf);
-  store4(wf, w[0] + off[0], w[1] + off[1], w[2] + off[2], w[3] + off[3]);
+  if (!abs_) {
+    float* wf = Wf + (int64_t)b * df + e;
+    const f32x4 w = load4(wf);
+    store4(wf, w[0] + off[0], w[1] + off[1], w[2] + off[2], w[3] + off[3]);
+  }
 }
 
 // ------------------------------------------------------------------ apply
@@ -742,14 +767,14 @@ hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int
 template <typename T>
 hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
                                     int B, int n, int d, int f, int Cs, int S, const uint8_t* docs, hipStream_t s) {
-  if (docs != nullptr && S != 1) return hipErrorInvalidValue;    // document resets run as one segment
   const int64_t tiles = cdiv(f, kWB) * cdiv(d, kWB) * B * S;
   if (tiles == 0) return hipSuccess;
   k_chunk_update_scan<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f, Cs, S, docs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t df = (int64_t)d * f;
-  k_scan_fixup<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(Wc, Wp, Tot, Wf, n / Cs, S, df);
+  k_scan_fixup<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(Wc, Wp, Tot, Wf, W0, docs, n / Cs,
+                                                                                  S, df);
   return hipGetLastError();
 }
 

@@ -138,8 +138,7 @@ int ttt_chunk_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, 
  *               chunk, i.e. the last document's.  NULL: one document per row,
  *               the same results as ttt_chunk_apply_update.
  * Same arguments, workspace and errors as ttt_chunk_apply_update otherwise
- * (the flags are read on the device; any byte value is valid).  The dot
- * update-scan then runs as one sequence segment. */
+ * (the flags are read on the device; any byte value is valid). */
 int ttt_chunk_apply_update_docs(const ttt_inplace_shape* shape, int dtype, int mode, float eta,
                                 const void* H, const void* X0, const void* W_gate, const void* W_up,
                                 const void* W_down0, const void* W_target, const void* conv_w,

@@ -228,13 +228,16 @@ def test_layer_chunk_synchronous_tile_order(mode):
 def test_layer_packed_documents(dtype, mode):
     """Rows packing several documents (ttt_chunk_apply_update_docs): at every flagged chunk the state restarts
     from W_down0 and the convolution from zeros, against the oracle with the same document starts.  Row 0 packs
-    documents of 3, 1 and 2 chunks, row 1 starts one at every chunk, row 2 holds a single document."""
+    documents of 2, 2 and 2 chunks, row 1 starts one at every chunk, row 2 holds a single document, row 3 two of
+    3 chunks.  With two sequence segments of 3 chunks in the fused dot plan, row 0's second segment starts inside a
+    document and resets in its middle, row 3's starts with a document."""
     eta = 0.05 if mode != "mse" else 0.5
-    cfg = small_cfg(dtype, mode, B=3, n=1536, d=264, f=392, C=256, eta=eta)
+    cfg = small_cfg(dtype, mode, B=4, n=1536, d=264, f=392, C=256, eta=eta)
     k = cfg.seq_len // cfg.chunk
-    starts = np.zeros((3, k), dtype=np.uint8)
-    starts[0, [0, 3, 4]] = 1
+    starts = np.zeros((4, k), dtype=np.uint8)
+    starts[0, [0, 2, 4]] = 1
     starts[1, :] = 1
+    starts[3, [0, 3]] = 1
     x = ti.inplace_inputs(cfg)
     g = dev(x)
     O, Wf = cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"],
@@ -246,7 +249,7 @@ def test_layer_packed_documents(dtype, mode):
                                    "dot" if mode == "dot_scan" else mode, doc_starts=starts)
     W0 = ti.to_f64(x["W_down0"])
     tol = TOL[dtype]
-    for b in range(3):
+    for b in range(4):
         assert rel(f64(O[b]), Oref[b]) < tol, b
         assert rel(f64(Wf[b]), Wref[b]) < tol and rel(f64(Wf[b]) - W0, Wref[b] - W0) < tol, b
 
@@ -436,3 +439,41 @@ def test_full_size_mse_first_chunks():
         for c in range(k):
             sl = slice(c * C, (c + 1) * C)
             assert rel(Ohead[b][sl], Oref[sl]) < TOL["bf16"], (b, c)
+
+
+@pytest.mark.slow
+def test_full_size_packed_documents_sampled():
+    """The 128K row packing 8 documents of 4 chunks, in the launch configuration the bench times: sampled rows of
+    chunk 4 (a document start: the plain gated MLP with W_down0) and chunk 5 (one update on chunk 4, whose
+    convolution starts from zeros), and sampled entries of W_final, which holds the last document alone."""
+    cfg = ti.workload("inplace_bf16_128k_8docs")
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    O, Wf = cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"],
+                                      g["conv_w"], cfg.chunk, cfg.eta, cfg.mode,
+                                      doc_starts=torch.from_numpy(cfg.doc_starts()).cuda())
+    torch.cuda.synchronize()
+    del g
+    C, d, f = cfg.chunk, cfg.d_model, cfg.d_ff
+    per = cfg.n_chunks // cfg.docs
+    H = ti.to_f64(x["H"])[0]
+    X0 = ti.to_f64(x["X0"])[0]
+    Wg, Wu, W0, Wt, cwt = (ti.to_f64(x[k]) for k in ("W_gate", "W_up", "W_down0", "W_target", "conv_w"))
+    rng = np.random.default_rng(1)
+    s4 = per * C                                             # first row of the second document
+    Z4 = orc.gated_intermediate(H[s4: s4 + C], Wg, Wu)
+    V4 = orc.target_values(X0[s4: s4 + C], cwt, Wt)          # zero-padded at the document start
+    W5 = W0 + cfg.eta * (V4.T @ Z4)
+    Og = f64(O[0])
+    rows4 = s4 + np.sort(rng.choice(C, 8, replace=False))
+    rows5 = s4 + C + np.sort(rng.choice(C, 8, replace=False))
+    assert rel(Og[rows4], Z4[rows4 - s4] @ W0.T) < TOL["bf16"]
+    assert rel(Og[rows5], orc.gated_intermediate(H[rows5], Wg, Wu) @ W5.T) < TOL["bf16"]
+    last = slice(cfg.seq_len - per * C, cfg.seq_len)         # the last document
+    ii, jj = rng.choice(d, 16), rng.choice(f, 16)
+    Hl, Xl = H[last], X0[last]
+    Zcols = orc.silu(Hl @ Wg[jj].T) * (Hl @ Wu[jj].T)
+    Vcols = orc.causal_depthwise_conv1d(Xl, cwt) @ Wt[:, ii]
+    ref = W0[ii, jj] + cfg.eta * np.sum(Vcols * Zcols, axis=0)
+    got = f64(Wf[0])[ii, jj]
+    assert rel(got, ref) < TOL["bf16"] and rel(got - W0[ii, jj], ref - W0[ii, jj]) < TOL["bf16"]

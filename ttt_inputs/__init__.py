@@ -53,10 +53,23 @@ class InplaceConfig:
     var_down: float | None = None    # default 1/d_ff
     var_target: float | None = None  # default 1/d_model
     var_conv: float = 0.25
+    docs: int = 1        # documents packed into each row, of equal length in chunks
 
     @property
     def tokens(self) -> int:
         return self.batch * self.seq_len
+
+    def doc_starts(self):
+        """Document-start flags [batch, n_chunks] (uint8: 1 where a document starts) for `docs` equal documents
+        per row, or None for one document per row."""
+        if self.docs <= 1:
+            return None
+        k = self.n_chunks
+        if k % self.docs:
+            raise ValueError(f"{k} chunks do not split into {self.docs} equal documents")
+        flags = np.zeros((self.batch, k), dtype=np.uint8)
+        flags[:, :: k // self.docs] = 1
+        return flags
 
     @property
     def n_chunks(self) -> int:
@@ -113,6 +126,9 @@ WORKLOADS = {
     "inplace_bf16_32k": InplaceConfig("inplace_bf16_32k", 1, 32768, 2560, 9728, 1024, 0.01, "dot", "bf16", seed=1001),
     "inplace_bf16_128k": InplaceConfig("inplace_bf16_128k", 1, 131072, 2560, 9728, 4096, 0.01, "dot", "bf16", seed=1002),
     "inplace_bf16_128k_c512": InplaceConfig("inplace_bf16_128k_c512", 1, 131072, 2560, 9728, 512, 0.01, "dot", "bf16", seed=1002),
+    # the 128K row packing 8 documents of 16K tokens (4 chunks each)
+    "inplace_bf16_128k_8docs": InplaceConfig("inplace_bf16_128k_8docs", 1, 131072, 2560, 9728, 4096, 0.01, "dot", "bf16",
+                                             seed=1002, docs=8),
     "mse_bf16_4x64k": InplaceConfig("mse_bf16_4x64k", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16", seed=1003),
     "lact_bf16_256k": LactConfig("lact_bf16_256k", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004),
 }
