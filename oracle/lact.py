@@ -60,10 +60,16 @@ def swiglu_grads(kc, vc, W1, W3, W2):
     return G1, G3, G2
 
 
-def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply"):
+def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply", update_mask=None):
     """LaCT layer over chunks.  q, k, v [B, H, n, dh]; W1, W3 [H, m, dh];
     W2 [H, dh, m].  Returns (O [B, H, n, dh], W1_f, W3_f [B, H, m, dh],
-    W2_f [B, H, dh, m])."""
+    W2_f [B, H, dh, m]).
+
+    `update_mask` [n_chunks] (truthy entries), if given, takes the update step
+    on the flagged chunks only; every chunk is applied.  With update-then-apply
+    this is the strided block-wise causal mask of the review's section on the
+    order of the apply and update operations (its video use updates on the
+    clean chunks only)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
     B, Hn, n, dh = q.shape
@@ -74,12 +80,13 @@ def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply"):
     for b in range(B):
         for h in range(Hn):
             w1, w3, w2 = W1[h].copy(), W3[h].copy(), W2[h].copy()
-            for s in range(0, n, chunk):
+            for c, s in enumerate(range(0, n, chunk)):
                 r = slice(s, min(s + chunk, n))
                 if order == "apply_then_update":
                     O[b, h, r] = swiglu_apply(q[b, h, r], w1, w3, w2)
-                g1, g3, g2 = swiglu_grads(k[b, h, r], v[b, h, r], w1, w3, w2)
-                w1, w3, w2 = w1 - eta * g1, w3 - eta * g3, w2 - eta * g2
+                if update_mask is None or update_mask[c]:
+                    g1, g3, g2 = swiglu_grads(k[b, h, r], v[b, h, r], w1, w3, w2)
+                    w1, w3, w2 = w1 - eta * g1, w3 - eta * g3, w2 - eta * g2
                 if order == "update_then_apply":
                     O[b, h, r] = swiglu_apply(q[b, h, r], w1, w3, w2)
                 elif order != "apply_then_update":

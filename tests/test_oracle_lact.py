@@ -135,3 +135,37 @@ def test_heads_and_batch_rows_are_independent():
                                            W1[h:h + 1], W3[h:h + 1], W2[h:h + 1], 4, 0.3)
             np.testing.assert_array_equal(O[b, h], Ob[0, 0])
             np.testing.assert_array_equal(W1f[b, h], W1b[0, 0])
+
+
+def test_update_mask_all_off_is_plain_swiglu():
+    """No chunk updates: every chunk is applied with the initial weights, which stay as they are."""
+    q, k, v, W1, W3, W2 = _problem(11)
+    n_chunks = q.shape[2] // 4
+    O, W1f, W3f, W2f = orc.lact_layer(q, k, v, W1, W3, W2, 4, 0.9, "update_then_apply",
+                                      update_mask=np.zeros(n_chunks, dtype=bool))
+    for h in range(W1.shape[0]):
+        ref = _torch_swiglu(torch.from_numpy(q[0, h]), torch.from_numpy(W1[h]), torch.from_numpy(W3[h]),
+                            torch.from_numpy(W2[h])).numpy()
+        np.testing.assert_allclose(O[0, h], ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(W1f[0], W1)
+    np.testing.assert_array_equal(W3f[0], W3)
+    np.testing.assert_array_equal(W2f[0], W2)
+
+
+@pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
+def test_update_mask_composes_from_unmasked_runs(order):
+    """Mask [1, 0, 1]: chunk 0 as an unmasked run, chunk 1 only applied (torch SwiGLU) with the weights chunk 0
+    left, chunk 2 as an unmasked run from those weights."""
+    q, k, v, W1, W3, W2 = _problem(12, H=1, n=12)
+    C, eta = 4, 0.6
+    O, W1f, W3f, W2f = orc.lact_layer(q, k, v, W1, W3, W2, C, eta, order, update_mask=[1, 0, 1])
+    r0, r1, r2 = slice(0, C), slice(C, 2 * C), slice(2 * C, 3 * C)
+    O0, a1, a3, a2 = orc.lact_layer(q[..., r0, :], k[..., r0, :], v[..., r0, :], W1, W3, W2, C, eta, order)
+    np.testing.assert_allclose(O[..., r0, :], O0, rtol=1e-12, atol=1e-14)
+    O1 = _torch_swiglu(torch.from_numpy(q[0, 0, r1]), torch.from_numpy(a1[0, 0]), torch.from_numpy(a3[0, 0]),
+                       torch.from_numpy(a2[0, 0])).numpy()
+    np.testing.assert_allclose(O[0, 0, r1], O1, rtol=1e-12, atol=1e-14)
+    O2, b1, b3, b2 = orc.lact_layer(q[..., r2, :], k[..., r2, :], v[..., r2, :], a1[0], a3[0], a2[0], C, eta, order)
+    np.testing.assert_allclose(O[..., r2, :], O2, rtol=1e-12, atol=1e-14)
+    for got, want in ((W1f, b1), (W3f, b3), (W2f, b2)):
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
