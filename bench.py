@@ -147,7 +147,7 @@ def bench_generic(cfg, steps, warmup):
         x = ti.lact_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
         call = lambda: cw.ttt_lact_swiglu(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta,
-                                          cfg.order)
+                                          cfg.order, update_mask=cfg.update_mask())
     else:
         x = ti.inplace_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
@@ -183,9 +183,11 @@ def cpu_baseline(cfg, target_s):
     cores = max([i.get("num_threads", 1) for i in info] + [1])
     if isinstance(cfg, ti.LactConfig):
         x = ti.lact_inputs(cfg)
+        umask = cfg.update_mask()
         run = lambda kc: olact.lact_layer(*(ti.to_f64(x[k][:, :1, : kc * cfg.chunk]) if k in "qkv"
                                             else ti.to_f64(x[k][:1]) for k in ("q", "k", "v", "W1", "W3", "W2")),
-                                          cfg.chunk, cfg.eta, cfg.order)
+                                          cfg.chunk, cfg.eta, cfg.order,
+                                          update_mask=None if umask is None else umask[:kc])
         per_tok_heads = 1
     else:
         x = ti.inplace_inputs(cfg)
@@ -251,6 +253,8 @@ def main():
         out["config"] = {"workload": cfg.name, "batch": cfg.batch, "heads": cfg.heads, "seq_len": cfg.seq_len,
                          "head_dim": cfg.head_dim, "hidden": cfg.hidden, "chunk": cfg.chunk, "eta": cfg.eta,
                          "order": cfg.order}
+        if cfg.update_every > 1:
+            out["config"]["update_every"] = cfg.update_every
     else:
         out["config"] = {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_len, "d_model": cfg.d_model,
                          "d_ff": cfg.d_ff, "chunk": cfg.chunk, "conv_k": cfg.conv_k, "eta": cfg.eta,

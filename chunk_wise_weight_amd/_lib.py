@@ -59,6 +59,8 @@ _SIGNATURES = {
     "ttt_lact_workspace_bytes": (_I, [ctypes.POINTER(LactShape), _I, ctypes.POINTER(_S)]),
     "ttt_lact_swiglu": (_I, [ctypes.POINTER(LactShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _S, _P]),
+    "ttt_lact_swiglu_masked": (_I, [ctypes.POINTER(LactShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                    _P, _P, _S, _P]),
 }
 
 _lib = None
@@ -340,8 +342,11 @@ def ttt_lact_workspace_bytes(shape: LactShape, dtype: torch.dtype) -> int:
 
 
 def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_then_apply", O=None, finals=None,
-                    workspace=None):
-    """LaCT SwiGLU layer.  Returns (O [B, H, n, dh], W1_f, W3_f [B, H, m, dh], W2_f [B, H, dh, m])."""
+                    workspace=None, update_mask=None):
+    """LaCT SwiGLU layer.  Returns (O [B, H, n, dh], W1_f, W3_f [B, H, m, dh], W2_f [B, H, dh, m]).
+
+    update_mask: optional host sequence of n // chunk flags; only the flagged chunks take the update step
+    (ttt_lact_swiglu_masked), every chunk is applied."""
     B, Hh, n, dh = q.shape
     m = W1.shape[1]
     dt, dev = q.dtype, q.device
@@ -362,7 +367,17 @@ def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_t
     nbytes = ttt_lact_workspace_bytes(shape, dt)
     ws = _workspace(nbytes, dev, workspace)
     ordc = _ORDERS[order] if isinstance(order, str) else int(order)
-    _check(lib().ttt_lact_swiglu(ctypes.byref(shape), _dt(dt), ordc, float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(W1),
-                                 _ptr(W3), _ptr(W2), _ptr(O), _ptr(W1f), _ptr(W3f), _ptr(W2f), _ptr(ws), nbytes,
-                                 _stream(dev)), "ttt_lact_swiglu")
+    if update_mask is None:
+        _check(lib().ttt_lact_swiglu(ctypes.byref(shape), _dt(dt), ordc, float(eta), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(W1), _ptr(W3), _ptr(W2), _ptr(O), _ptr(W1f), _ptr(W3f), _ptr(W2f),
+                                     _ptr(ws), nbytes, _stream(dev)), "ttt_lact_swiglu")
+        return O, W1f, W3f, W2f
+    flags = [1 if bool(x) else 0 for x in (update_mask.tolist() if hasattr(update_mask, "tolist") else update_mask)]
+    if chunk <= 0 or len(flags) != n // chunk:
+        raise ValueError(f"update_mask needs {n // chunk if chunk > 0 else 0} entries, got {len(flags)}")
+    mask = (ctypes.c_ubyte * max(1, len(flags)))(*flags)
+    _check(lib().ttt_lact_swiglu_masked(ctypes.byref(shape), _dt(dt), ordc, float(eta), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(W1), _ptr(W3), _ptr(W2), ctypes.cast(mask, ctypes.c_void_p), _ptr(O),
+                                        _ptr(W1f), _ptr(W3f), _ptr(W2f), _ptr(ws), nbytes, _stream(dev)),
+           "ttt_lact_swiglu_masked")
     return O, W1f, W3f, W2f

@@ -487,6 +487,14 @@ int ttt_lact_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* byt
 int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta, const void* q, const void* k,
                     const void* v, const void* W1, const void* W3, const void* W2, void* O, float* W1_f, float* W3_f,
                     float* W2_f, void* workspace, size_t workspace_bytes, void* stream) {
+  return ttt_lact_swiglu_masked(shape, dtype, order, eta, q, k, v, W1, W3, W2, nullptr, O, W1_f, W3_f, W2_f,
+                                workspace, workspace_bytes, stream);
+}
+
+int ttt_lact_swiglu_masked(const ttt_lact_shape* shape, int dtype, int order, float eta, const void* q,
+                           const void* k, const void* v, const void* W1, const void* W3, const void* W2,
+                           const unsigned char* update_mask, void* O, float* W1_f, float* W3_f, float* W2_f,
+                           void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_lact(shape, dtype);
   if (st != TTT_OK) return st;
   if (order != TTT_UPDATE_THEN_APPLY && order != TTT_APPLY_THEN_UPDATE) return TTT_ERR_ARG;
@@ -500,7 +508,8 @@ int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta
   const size_t need = dtype == TTT_BF16 ? ttt::lact_workspace_bytes<bf16>(B, H, n, dh, m, C)
                                         : ttt::lact_workspace_bytes<float>(B, H, n, dh, m, C);
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)) return TTT_ERR_WORKSPACE;
-  ttt::LactArgs a{B, H, n, dh, m, C, order, eta, q, k, v, W1, W3, W2, O, W1_f, W3_f, W2_f, (char*)workspace};
+  ttt::LactArgs a{B, H, n, dh, m, C, order, eta, q, k, v, W1, W3, W2, O, W1_f, W3_f, W2_f, (char*)workspace,
+                  update_mask};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == TTT_BF16 ? ttt::launch_lact<bf16>(a, s) : ttt::launch_lact<float>(a, s);
   if (e == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;

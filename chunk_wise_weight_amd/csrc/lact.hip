@@ -545,6 +545,8 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
       sr.qc = sr.kc = c;
       sr.nq = sr.nk = C;
     }
+    if (sr.nk > 0 && a.update_mask != nullptr && a.update_mask[sr.kc] == 0) sr.nk = 0;   // applied only
+    if (sr.nq == 0 && sr.nk == 0) continue;
     const int tq1 = (int)(cdiv(sr.nq, Wide::BQ) + cdiv(sr.nk, Wide::BQ));
     if (want()) k_lact_fwd1<T><<<(unsigned)(cdiv(m, Wide::BP / 2) * tq1 * BH), Wide::NT, 0, s>>>(q, kk, W1s, W3s, Hh, A, U, BH, n,
                                                                                    dh, m, C, sr);

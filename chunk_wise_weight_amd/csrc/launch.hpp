@@ -67,6 +67,7 @@ struct LactArgs {
   void* O;
   float *W1f, *W3f, *W2f;
   char* ws;
+  const unsigned char* update_mask;   // HOST [n / C]: chunks whose keys update the weights; null = every chunk
 };
 template <typename T>
 size_t lact_workspace_bytes(int B, int H, int n, int dh, int m, int C);

@@ -250,6 +250,25 @@ int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta
                     void* O, float* W1_f, float* W3_f, float* W2_f,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* The same layer with a strided update (review of "Test-Time Training Done
+ * Right", LaCT Model Architecture §1 on the order of the apply and update
+ * operations: updating on some chunks only while applying all of them gives a
+ * strided block-wise causal mask; its video use updates on clean chunks).
+ *   update_mask  [n / chunk] uint8, HOST memory read during the call, shared
+ *                by every (batch, head) row: chunk c's keys and values take
+ *                the gradient step only where update_mask[c] != 0; every
+ *                chunk's queries are applied.  NULL: every chunk updates
+ *                (ttt_lact_swiglu).  The mask decides which launches are
+ *                enqueued, so a captured graph keeps the mask it was
+ *                captured with.
+ * Same arguments, workspace and errors as ttt_lact_swiglu otherwise. */
+int ttt_lact_swiglu_masked(const ttt_lact_shape* shape, int dtype, int order, float eta,
+                           const void* q, const void* k, const void* v,
+                           const void* W1, const void* W3, const void* W2,
+                           const unsigned char* update_mask,
+                           void* O, float* W1_f, float* W3_f, float* W2_f,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

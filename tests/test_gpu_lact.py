@@ -103,6 +103,34 @@ def test_lact_rows_equal_single_row_calls(B, H):
                 assert torch.equal(got[0, 0], want[b, h]), (b, h)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
+def test_lact_update_mask(dtype, order):
+    """Strided update (ttt_lact_swiglu_masked): only the flagged chunks take the gradient step, every chunk is
+    applied, against the oracle with the same mask on 2 x 2 rows (both stream groups); the first chunk is masked,
+    which leaves the first update-then-apply step with nothing to do.  An all-on mask gives the unmasked call's
+    bits."""
+    cfg = cfg_small(dtype, order, B=2, H=2, n=768, dh=64, m=128, C=128, eta=0.8, seed=21)
+    mask = [0, 1, 1, 0, 1, 0]
+    x = ti.lact_inputs(cfg)
+    g = {k: v.cuda() for k, v in x.items()}
+    args = (g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta, cfg.order)
+    got = cw.ttt_lact_swiglu(*args, update_mask=mask)
+    plain = cw.ttt_lact_swiglu(*args)
+    all_on = cw.ttt_lact_swiglu(*args, update_mask=[1] * len(mask))
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(all_on, plain))
+    Oref, W1r, W3r, W2r = olact.lact_layer(*(ti.to_f64(x[k]) for k in ("q", "k", "v", "W1", "W3", "W2")), cfg.chunk,
+                                           cfg.eta, cfg.order, update_mask=mask)
+    tol = TOL[dtype]
+    errs = {"O": rel(f64(got[0]), Oref)}
+    for name, t, want, init in (("W1", got[1], W1r, x["W1"]), ("W3", got[2], W3r, x["W3"]), ("W2", got[3], W2r, x["W2"])):
+        w0 = ti.to_f64(init)[None]
+        errs[name] = rel(f64(t), want)
+        errs[name + "_delta"] = rel(f64(t) - w0, want - w0)
+    assert all(e < tol for e in errs.values()), errs
+
+
 def test_lact_single_chunk_full_batch_step():
     cfg = cfg_small("f32", n=256, C=256)
     check(cfg, *run(cfg))

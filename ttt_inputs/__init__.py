@@ -102,19 +102,29 @@ class LactConfig:
     var_w1: float | None = None   # default 1/head_dim
     var_w3: float | None = None   # default 1/head_dim
     var_w2: float | None = None   # default 1/hidden
+    update_every: int = 1         # only every update_every-th chunk takes the update step (1: all)
 
     @property
     def tokens(self) -> int:
         return self.batch * self.seq_len
+
+    def update_mask(self):
+        """Per-chunk update flags (list of 0/1) when only every update_every-th chunk updates, else None."""
+        if self.update_every <= 1:
+            return None
+        return [1 if c % self.update_every == 0 else 0 for c in range(self.n_chunks)]
 
     @property
     def n_chunks(self) -> int:
         return self.seq_len // self.chunk
 
     def flops(self) -> float:
-        """Algorithmic flops: per token per head, key forward 6*dh*m,
-        backward 8*dh*m (dH, G1, G2, G3), query apply 6*dh*m."""
-        return float(self.tokens) * self.heads * 20.0 * self.head_dim * self.hidden
+        """Algorithmic flops: per token per head, key forward 6*dh*m and
+        backward 8*dh*m (dH, G1, G2, G3) on the chunks that update, query apply
+        6*dh*m on every chunk."""
+        mask = self.update_mask()
+        upd = 1.0 if mask is None else sum(mask) / len(mask)
+        return float(self.tokens) * self.heads * (6.0 + 14.0 * upd) * self.head_dim * self.hidden
 
     def with_(self, **kw) -> "LactConfig":
         return replace(self, **kw)
@@ -131,6 +141,9 @@ WORKLOADS = {
                                              seed=1002, docs=8),
     "mse_bf16_4x64k": InplaceConfig("mse_bf16_4x64k", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16", seed=1003),
     "lact_bf16_256k": LactConfig("lact_bf16_256k", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004),
+    # the same with the update on every other chunk only (a strided block-wise mask)
+    "lact_bf16_256k_strided": LactConfig("lact_bf16_256k_strided", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
+                                         update_every=2),
 }
 
 
