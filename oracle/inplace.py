@@ -44,7 +44,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "silu", "causal_depthwise_conv1d", "target_values", "gated_intermediate",
+    "silu", "causal_depthwise_conv1d", "forward_chunk_conv1d", "target_values", "gated_intermediate",
     "gated_mlp", "loss_dot", "loss_mse", "grad_dot", "grad_mse",
     "chunk_apply_update", "chunk_prefix_form", "inplace_layer",
 ]
@@ -78,6 +78,31 @@ def causal_depthwise_conv1d(X0, conv_w):
         if back >= n:
             continue
         Y[..., back:, :] += conv_w[:, j] * X0[..., : n - back, :]
+    return Y
+
+
+def forward_chunk_conv1d(X0, conv_w, chunk):
+    """The forward-looking reading of the convolution (the review's next-token
+    example, Method §2): within each chunk, tap j multiplies the token j steps
+    ahead, and tokens past the chunk's end are zero, so a chunk's targets come
+    from its own tokens only and the per-chunk step stays causal at chunk level.
+    With W_target = I and conv_w[:, 1] = 1 (all other taps 0) the target of a
+    token is the next token's embedding, except at a chunk's last token.
+
+    X0: [..., n, d]; conv_w: [d, K].  Y[t, ch] = sum_j conv_w[ch, j] *
+    X0[t + j, ch] for t + j inside t's chunk.
+    """
+    X0 = _f64(X0)
+    conv_w = _f64(conv_w)
+    n = X0.shape[-2]
+    K = conv_w.shape[1]
+    Y = np.zeros_like(X0)
+    for s in range(0, n, chunk):
+        e = min(s + chunk, n)
+        for j in range(K):
+            if j >= e - s:
+                continue
+            Y[..., s: e - j, :] += conv_w[:, j] * X0[..., s + j: e, :]
     return Y
 
 
@@ -165,7 +190,7 @@ def chunk_prefix_form(Z, Vhat, W0, chunk, eta):
 
 
 def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
-                  mode, max_chunks=None, x0_halo=None, doc_starts=None):
+                  mode, max_chunks=None, x0_halo=None, doc_starts=None, conv_forward=False):
     """The whole In-Place TTT layer, one document per batch row.
 
     H, X0 [B, n, d]; W_gate, W_up [f, d]; W_down0 [d, f]; W_target [d, d];
@@ -177,6 +202,10 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
     row: a document starts at every flagged chunk c > 0 (chunk 0 always starts
     one), where the state is reset to W_down0 and the convolution restarts
     with zeros before the chunk's first row (Method §3, document boundaries).
+
+    `conv_forward` takes the forward-looking in-chunk convolution
+    (forward_chunk_conv1d) for the target; it reads no row outside the chunk,
+    so `x0_halo` and document starts do not change it.
 
     `max_chunks` stops after that many chunks (O then covers only those rows
     and W_final is the state after them) -- used to time a bounded sample.
@@ -208,7 +237,10 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
                 W = _f64(W_down0).copy()   # a packed document starts here
                 doc_row = s + off
             lo = max(doc_row, s + off - (K - 1))
-            Y = causal_depthwise_conv1d(Xfull[lo: e + off], conv_w)[-(e - s):]
+            if conv_forward:
+                Y = forward_chunk_conv1d(Xfull[s + off: e + off], conv_w, e - s)
+            else:
+                Y = causal_depthwise_conv1d(Xfull[lo: e + off], conv_w)[-(e - s):]
             Vc = Y @ W_target
             Zc = gated_intermediate(H[b, s:e], W_gate, W_up)
             O[b, s:e] = Zc @ W.T

@@ -444,3 +444,54 @@ def test_planted_mistakes_fail_the_pins(monkeypatch):
     monkeypatch.setitem(orc._GRADS, "mse", lambda W, Zc, Vc: (Zc @ W.T - Vc).T @ Zc)  # no 1/C
     _, W = orc.chunk_apply_update(Zs, Vs, Ws, gm["chunk"], gm["eta"], "mse")
     assert not np.allclose(W, np.array(gm["W_final"], float))
+
+
+def test_forward_conv_next_token_example():
+    """The review's next-token target (Method §2): W_target = I and a kernel that weights only the next token give
+    each token the next token's embedding; with the forward-looking in-chunk reading, a chunk's last token gets
+    zero (the next token belongs to the next chunk)."""
+    rng = _rng(30)
+    n, C, d, K = 12, 4, 3, 4
+    X0 = rng.standard_normal((n, d))
+    cw = np.zeros((d, K))
+    cw[:, 1] = 1.0
+    V = orc.forward_chunk_conv1d(X0, cw, C) @ np.eye(d)
+    want = np.zeros((n, d))
+    for t in range(n):
+        if (t + 1) % C:
+            want[t] = X0[t + 1]
+    np.testing.assert_array_equal(V, want)
+
+
+@pytest.mark.parametrize("n,C,d,K", [(12, 4, 3, 4), (10, 5, 2, 3), (8, 8, 4, 1)])
+def test_forward_conv_matches_torch_per_chunk(n, C, d, K):
+    """Per chunk, torch's depthwise conv1d (a cross-correlation) with K-1 zeros appended on the right."""
+    rng = _rng(31)
+    X0 = rng.standard_normal((n, d))
+    cw = rng.standard_normal((d, K))
+    Y = orc.forward_chunk_conv1d(X0, cw, C)
+    for s in range(0, n, C):
+        x = torch.from_numpy(X0[s:s + C].T.copy())[None]                      # [1, d, C]
+        ref = F.conv1d(F.pad(x, (0, K - 1)), torch.from_numpy(cw)[:, None, :], groups=d)[0].T.numpy()
+        np.testing.assert_allclose(Y[s:s + C], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_forward_conv_layer_is_causal_per_chunk_and_composes(mode):
+    """With the forward-looking target, chunk c's update reads chunk c's tokens only: changing X0 in chunks >= c
+    leaves the outputs of chunks <= c unchanged.  The streamed layer equals the chunk loop on the whole-sequence
+    target."""
+    rng = _rng(32)
+    n, C, d, f, K = 24, 6, 4, 5, 4
+    H, X0, Wg, Wu, W0, Wt, cw = _problem(rng, n, d, f, K)
+    O, Wf = orc.inplace_layer(H[None], X0[None], Wg, Wu, W0, Wt, cw, C, 0.1, mode, conv_forward=True)
+    Z = orc.gated_intermediate(H, Wg, Wu)
+    V = orc.forward_chunk_conv1d(X0, cw, C) @ Wt
+    O2, W2 = orc.chunk_apply_update(Z, V, W0, C, 0.1, mode)
+    np.testing.assert_allclose(O[0], O2, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Wf[0], W2, rtol=1e-12, atol=1e-12)
+    for c in range(n // C):
+        X0p = X0.copy()
+        X0p[c * C:] += rng.standard_normal(X0p[c * C:].shape)
+        Op, _ = orc.inplace_layer(H[None], X0p[None], Wg, Wu, W0, Wt, cw, C, 0.1, mode, conv_forward=True)
+        np.testing.assert_array_equal(Op[0, : (c + 1) * C], O[0, : (c + 1) * C])
