@@ -155,7 +155,7 @@ def bench_generic(cfg, steps, warmup):
         docs = None if flags is None else torch.from_numpy(flags).cuda()
         call = lambda: cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"],
                                                  g["W_target"], g["conv_w"], cfg.chunk, cfg.eta, cfg.mode,
-                                                 doc_starts=docs)
+                                                 doc_starts=docs, conv_forward=cfg.conv_forward)
     for _ in range(warmup):
         call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -197,7 +197,8 @@ def cpu_baseline(cfg, target_s):
                                            ti.to_f64(x["X0"][:1, : kc * cfg.chunk]), ws["W_gate"], ws["W_up"],
                                            ws["W_down0"], ws["W_target"], ws["conv_w"], cfg.chunk, cfg.eta,
                                            "dot" if cfg.mode == "dot_scan" else cfg.mode,
-                                           doc_starts=None if flags is None else flags[:1, :kc])
+                                           doc_starts=None if flags is None else flags[:1, :kc],
+                                           conv_forward=cfg.conv_forward)
     t0 = time.perf_counter()
     run(1)
     t1 = time.perf_counter() - t0
@@ -261,8 +262,10 @@ def main():
                          "mode": cfg.mode}
         if cfg.docs > 1:
             out["config"]["docs_per_row"] = cfg.docs
+        if cfg.conv_forward:
+            out["config"]["conv"] = "forward in-chunk"
 
-    if not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot" and cfg.docs == 1:
+    if not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot" and cfg.docs == 1 and not cfg.conv_forward:
         wall, per, _ = bench_inplace_dot(cfg, args.steps, args.warmup)
         fl, by = kernel_flops(cfg), kernel_bytes(cfg, 2 if dtype == "bf16" else 4)
         kern = {}

@@ -26,6 +26,10 @@ class InplaceShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("batch", "seq_len", "d_model", "d_ff", "chunk", "conv_k")]
 
 
+class LayerOptions(ctypes.Structure):
+    _fields_ = [("doc_starts", ctypes.c_void_p), ("conv_forward", ctypes.c_int)]
+
+
 class LactShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("batch", "heads", "seq_len", "head_dim", "hidden", "chunk")]
 
@@ -45,8 +49,8 @@ _SIGNATURES = {
     "ttt_inplace_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _I, ctypes.POINTER(_S)]),
     "ttt_chunk_apply_update": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                     _P, _S, _P]),
-    "ttt_chunk_apply_update_docs": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P,
-                                         _P, _P, _P, _S, _P]),
+    "ttt_chunk_apply_update_ex": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P,
+                                       ctypes.POINTER(LayerOptions), _P, _P, _P, _S, _P]),
     "ttt_core_apply_update": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _S, _P]),
     "ttt_produce_z": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P, _P]),
     "ttt_vhat_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, ctypes.POINTER(_S)]),
@@ -149,11 +153,12 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk: int, eta: float, mode="dot",
-                           O=None, W_final=None, workspace=None, doc_starts=None):
+                           O=None, W_final=None, workspace=None, doc_starts=None, conv_forward=False):
     """The whole In-Place layer.  Returns (O [B, n, d], W_final [B, d, f] fp32).
 
-    doc_starts: optional uint8 (or bool) device tensor [B, seq_len // chunk] whose nonzero entries mark the
-    chunks that start a new document in their row (ttt_chunk_apply_update_docs)."""
+    Options (ttt_chunk_apply_update_ex): doc_starts, a uint8 (or bool) device tensor [B, seq_len // chunk] whose
+    nonzero entries mark the chunks that start a new document in their row; conv_forward, the forward-looking
+    in-chunk convolution for the target."""
     B, n, d = H.shape
     f = W_gate.shape[0]
     K = conv_w.shape[1]
@@ -169,20 +174,23 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
     _need(W_final, "W_final", (B, d, f), torch.float32, dev)
     nbytes = ttt_inplace_workspace_bytes(shape, dt, mode, True)
     ws = _workspace(nbytes, dev, workspace)
-    if doc_starts is None:
+    if doc_starts is None and not conv_forward:
         _check(lib().ttt_chunk_apply_update(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
                                             _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
                                             _ptr(conv_w), _ptr(O), _ptr(W_final), _ptr(ws), nbytes, _stream(dev)),
                "ttt_chunk_apply_update")
         return O, W_final
-    if doc_starts.dtype == torch.bool:
-        doc_starts = doc_starts.to(torch.uint8)
-    _need(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), torch.uint8, dev)
-    _check(lib().ttt_chunk_apply_update_docs(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
-                                             _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
-                                             _ptr(conv_w), _ptr(doc_starts), _ptr(O), _ptr(W_final), _ptr(ws),
-                                             nbytes, _stream(dev)),
-           "ttt_chunk_apply_update_docs")
+    if doc_starts is not None:
+        if doc_starts.dtype == torch.bool:
+            doc_starts = doc_starts.to(torch.uint8)
+        _need(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), torch.uint8, dev)
+    opts = LayerOptions(ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None else None,
+                        1 if conv_forward else 0)
+    _check(lib().ttt_chunk_apply_update_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
+                                           _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
+                                           _ptr(conv_w), ctypes.byref(opts), _ptr(O), _ptr(W_final), _ptr(ws),
+                                           nbytes, _stream(dev)),
+           "ttt_chunk_apply_update_ex")
     return O, W_final
 
 

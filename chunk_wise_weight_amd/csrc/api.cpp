@@ -28,6 +28,7 @@ struct Plan {
   // workspace regions (byte offsets); Y and WtT only with the producers
   size_t off_Y, off_WtT, off_Zt, off_Vt, off_Wc, off_dW, off_Wp, off_Tot, off_Rt, off_Wsh, total;
   const uint8_t* docs;  // document starts [B, k] (device) or null: one document per batch row
+  bool conv_fwd;        // forward-looking in-chunk convolution for the target
 };
 
 int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
@@ -54,6 +55,7 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   if (st != TTT_OK) return st;
   if (mode != TTT_MODE_DOT && mode != TTT_MODE_MSE && mode != TTT_MODE_DOT_SCAN) return TTT_ERR_ARG;
   p->docs = nullptr;
+  p->conv_fwd = false;
   p->B = s->batch;
   p->n = s->seq_len;
   p->d = s->d_model;
@@ -165,7 +167,8 @@ int run_producers(const Plan& p, const void* H, const void* X0, const void* Wg, 
   T* Y = (T*)(ws + p.off_Y);
   T* WtT = (T*)(ws + p.off_WtT);
   int st = dev(ttt::launch_produce_z<T>((const T*)H, (const T*)Wg, (const T*)Wu, nullptr, Zt, rows, n, d, f, s));
-  if (st == TTT_OK) st = dev(ttt::launch_conv<T>((const T*)X0, (const T*)cw, Y, rows, n, d, (int)p.K, p.docs, (int)p.C, s));
+  if (st == TTT_OK) st = dev(ttt::launch_conv<T>((const T*)X0, (const T*)cw, Y, rows, n, d, (int)p.K, p.docs, (int)p.C,
+                                                  p.conv_fwd, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Wt, WtT, 1, d, d, 1.0f, s));
   if (st == TTT_OK) st = dev(ttt::launch_produce_vhat<T>(Y, WtT, Vt, rows, n, d, vscale, s));
   return st;
@@ -250,10 +253,10 @@ int ttt_chunk_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, 
   return layer<float>(p, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, ws, s);
 }
 
-int ttt_chunk_apply_update_docs(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* H,
-                                const void* X0, const void* W_gate, const void* W_up, const void* W_down0,
-                                const void* W_target, const void* conv_w, const unsigned char* doc_starts, void* O,
-                                float* W_final, void* workspace, size_t workspace_bytes, void* stream) {
+int ttt_chunk_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* H,
+                              const void* X0, const void* W_gate, const void* W_up, const void* W_down0,
+                              const void* W_target, const void* conv_w, const ttt_layer_options* options, void* O,
+                              float* W_final, void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
   int st = make_plan(shape, dtype, mode, true, &p);
   if (st != TTT_OK) return st;
@@ -265,7 +268,11 @@ int ttt_chunk_apply_update_docs(const ttt_inplace_shape* shape, int dtype, int m
       return TTT_ERR_ARG;
   }
   if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
-  p.docs = doc_starts;
+  if (options != nullptr) {
+    if (options->conv_forward != 0 && options->conv_forward != 1) return TTT_ERR_ARG;
+    p.docs = options->doc_starts;
+    p.conv_fwd = options->conv_forward == 1;
+  }
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if (dtype == TTT_BF16)
@@ -340,7 +347,7 @@ int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, float scale, con
   const int n = (int)p.n, d = (int)p.d, K = (int)p.K;
   if (dtype == TTT_BF16) {
     st = dev(ttt::launch_conv<bf16>((const bf16*)X0, (const bf16*)conv_w, (bf16*)(ws + p.off_Y), rows, n, d, K, nullptr,
-                                    (int)p.C, s));
+                                    (int)p.C, false, s));
     if (st == TTT_OK)
       st = dev(ttt::launch_transpose<bf16>((const bf16*)W_target, (bf16*)(ws + p.off_WtT), 1, d, d, 1.0f, s));
     if (st == TTT_OK)
@@ -349,7 +356,7 @@ int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, float scale, con
     return st;
   }
   st = dev(ttt::launch_conv<float>((const float*)X0, (const float*)conv_w, (float*)(ws + p.off_Y), rows, n, d, K,
-                                   nullptr, (int)p.C, s));
+                                   nullptr, (int)p.C, false, s));
   if (st == TTT_OK)
     st = dev(ttt::launch_transpose<float>((const float*)W_target, (float*)(ws + p.off_WtT), 1, d, d, 1.0f, s));
   if (st == TTT_OK)

@@ -31,7 +31,10 @@ template <typename T> constexpr int esz() { return (int)sizeof(T); }
 // chunk, reading each of the RW + KW - 1 input rows it needs once (a sliding
 // window; RW divides n, so a thread's rows never straddle a batch row).
 constexpr int kConvRows = 8;
-template <typename T, int KW>
+// FWD: the forward-looking in-chunk reading -- tap j multiplies the token j
+// steps ahead, and tokens past the chunk's end are zero (the review's
+// next-token example, Method §2); else tap KW - 1 is the current token.
+template <typename T, int KW, bool FWD>
 __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T* __restrict__ cw, T* __restrict__ Y,
                                               int64_t rows, int n, int d, const uint8_t* __restrict__ docs, int C_) {
   constexpr int V = Vec<T>::V, RW = kConvRows, NIN = RW + KW - 1;
@@ -41,8 +44,10 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
   const int ch = (int)(gid % nchunk) * V;
   const int64_t r0 = (gid / nchunk) * RW;
   const int pos0 = (int)(r0 % n);                  // position of row r0 in its sequence
-  // first row of its document: the thread's rows lie in one chunk (C_ % 8 == 0)
+  // first row of its document, and the end of its chunk: the thread's rows lie
+  // in one chunk (C_ % 8 == 0)
   const int lo = doc_start(docs, r0 / n, n / C_, pos0 / C_) ? (pos0 / C_) * C_ : 0;
+  const int hi = (pos0 / C_ + 1) * C_;
   float w[V][KW];
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(cw + (int64_t)ch * KW);
@@ -59,14 +64,15 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
       for (int e = 0; e < V; ++e) w[(c * V + e) / KW][(c * V + e) % KW] = fv[e];
     }
   }
-  // input row i of the window is X0 row r0 - (KW - 1) + i; rows before the
-  // document start are zero
+  // input row i of the window is X0 row r0 - (KW - 1) + i (FWD: r0 + i); rows
+  // before the document start (FWD: from the chunk's end on) are zero
   u32x4 in[NIN];
-  const T* base = X0 + (r0 - (KW - 1)) * d + ch;
+  const T* base = X0 + (r0 - (FWD ? 0 : KW - 1)) * d + ch;
 #pragma unroll
-  for (int i = 0; i < NIN; ++i)
-    in[i] = (i >= KW - 1 || pos0 + i - (KW - 1) >= lo) ? *reinterpret_cast<const u32x4*>(base + (int64_t)i * d)
-                                                      : u32x4{0u, 0u, 0u, 0u};
+  for (int i = 0; i < NIN; ++i) {
+    const bool live = FWD ? (i < RW || pos0 + i < hi) : (i >= KW - 1 || pos0 + i - (KW - 1) >= lo);
+    in[i] = live ? *reinterpret_cast<const u32x4*>(base + (int64_t)i * d) : u32x4{0u, 0u, 0u, 0u};
+  }
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     float y[V];
@@ -712,12 +718,16 @@ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <typename T>
 hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, const uint8_t* docs, int C,
-                       hipStream_t s) {
+                       bool fwd, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int64_t threads = (rows / kConvRows) * (d / Vec<T>::V);     // rows % kConvRows == 0 (n % 8 == 0)
   const dim3 g((unsigned)cdiv(threads, 256));
   switch (K) {
-#define TTT_KW(KW) case KW: k_conv<T, KW><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d, docs, C); break;
+#define TTT_KW(KW)                                                                                            \
+  case KW:                                                                                                    \
+    if (fwd) k_conv<T, KW, true><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d, docs, C);                         \
+    else k_conv<T, KW, false><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d, docs, C);                            \
+    break;
     TTT_KW(1) TTT_KW(2) TTT_KW(3) TTT_KW(4) TTT_KW(5) TTT_KW(6) TTT_KW(7) TTT_KW(8)
 #undef TTT_KW
     default: return hipErrorInvalidValue;
@@ -801,7 +811,7 @@ hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur
 }
 
 #define TTT_INST(T)                                                                                               \
-  template hipError_t launch_conv<T>(const T*, const T*, T*, int64_t, int, int, int, const uint8_t*, int,        \
+  template hipError_t launch_conv<T>(const T*, const T*, T*, int64_t, int, int, int, const uint8_t*, int, bool,  \
                                      hipStream_t);                                                                \
   template hipError_t launch_transpose<T>(const T*, T*, int, int, int, float, hipStream_t);                      \
   template hipError_t launch_produce_z<T>(const T*, const T*, const T*, T*, T*, int64_t, int, int, int,          \

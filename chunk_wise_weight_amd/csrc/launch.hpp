@@ -10,7 +10,7 @@ typedef __bf16 bf16;
 
 template <typename T>
 hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, const uint8_t* docs, int C,
-                       hipStream_t s);
+                       bool fwd, hipStream_t s);
 template <typename T>
 hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int C, float scale, hipStream_t s);
 template <typename T>

@@ -125,25 +125,37 @@ int ttt_chunk_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, 
                            void* O, float* W_final, void* workspace, size_t workspace_bytes,
                            void* stream);
 
-/* The same layer over rows that pack several documents (In-Place TTT review,
- * Method §3: the fast weight is reset to the pretrained state at document
- * boundaries, so that no context leaks between independent sequences).
- *   doc_starts  [B, k] uint8, DEVICE, k = seq_len / chunk: a nonzero entry
- *               marks chunk c as the first chunk of a document (entry 0 of a
- *               row is implied).  Documents therefore start at chunk
- *               boundaries.  At a document start the state is W_down0 again
- *               (chunk c is applied with W_down0 and updates it) and the
- *               convolution restarts: rows before the chunk's first token
- *               read as zero.  W_final is the state after the row's last
- *               chunk, i.e. the last document's.  NULL: one document per row,
- *               the same results as ttt_chunk_apply_update.
- * Same arguments, workspace and errors as ttt_chunk_apply_update otherwise
- * (the flags are read on the device; any byte value is valid). */
-int ttt_chunk_apply_update_docs(const ttt_inplace_shape* shape, int dtype, int mode, float eta,
-                                const void* H, const void* X0, const void* W_gate, const void* W_up,
-                                const void* W_down0, const void* W_target, const void* conv_w,
-                                const unsigned char* doc_starts, void* O, float* W_final,
-                                void* workspace, size_t workspace_bytes, void* stream);
+/* Options of ttt_chunk_apply_update_ex; a NULL options pointer, or all fields
+ * zero, gives ttt_chunk_apply_update's results. */
+typedef struct {
+  /* Rows that pack several documents (In-Place TTT review, Method §3: the
+   * fast weight is reset to the pretrained state at document boundaries, so
+   * that no context leaks between independent sequences).  [B, k] uint8,
+   * DEVICE, k = seq_len / chunk: a nonzero entry marks chunk c as the first
+   * chunk of a document (entry 0 of a row is implied), so documents start at
+   * chunk boundaries.  At a document start the state is W_down0 again (chunk
+   * c is applied with W_down0 and updates it) and the convolution restarts:
+   * rows before the chunk's first token read as zero.  W_final is the state
+   * after the row's last chunk, i.e. the last document's.  Read on the
+   * device; any byte value is valid.  NULL: one document per row. */
+  const unsigned char* doc_starts;
+  /* 0: the causal convolution of ttt_chunk_apply_update.  1: the forward-
+   * looking in-chunk reading of the review's next-token example (Method §2):
+   * tap j multiplies the token j steps ahead and tokens past the end of the
+   * token's chunk are zero, so a chunk's targets come from its own tokens and
+   * its update stays causal at chunk level; with W_target = I and
+   * conv_w[:, 1] = 1 the target of a token is the next token (zero at a
+   * chunk's last token).  Other values: TTT_ERR_ARG. */
+  int conv_forward;
+} ttt_layer_options;
+
+/* The layer of ttt_chunk_apply_update with options (above); same arguments,
+ * workspace and errors otherwise. */
+int ttt_chunk_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mode, float eta,
+                              const void* H, const void* X0, const void* W_gate, const void* W_up,
+                              const void* W_down0, const void* W_target, const void* conv_w,
+                              const ttt_layer_options* options, void* O, float* W_final,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* The chunk loop alone, given Z [B, n, f] and Vhat [B, n, d] (dtype) instead
  * of the producers' inputs.  Same outputs and rules as above; workspace from

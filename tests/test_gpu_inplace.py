@@ -226,7 +226,7 @@ def test_layer_chunk_synchronous_tile_order(mode):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["dot", "dot_scan", "mse"])
 def test_layer_packed_documents(dtype, mode):
-    """Rows packing several documents (ttt_chunk_apply_update_docs): at every flagged chunk the state restarts
+    """Rows packing several documents (ttt_chunk_apply_update_ex): at every flagged chunk the state restarts
     from W_down0 and the convolution from zeros, against the oracle with the same document starts.  Row 0 packs
     documents of 2, 2 and 2 chunks, row 1 starts one at every chunk, row 2 holds a single document, row 3 two of
     3 chunks.  With two sequence segments of 3 chunks in the fused dot plan, row 0's second segment starts inside a
@@ -250,6 +250,33 @@ def test_layer_packed_documents(dtype, mode):
     W0 = ti.to_f64(x["W_down0"])
     tol = TOL[dtype]
     for b in range(4):
+        assert rel(f64(O[b]), Oref[b]) < tol, b
+        assert rel(f64(Wf[b]), Wref[b]) < tol and rel(f64(Wf[b]) - W0, Wref[b] - W0) < tol, b
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["dot", "dot_scan", "mse"])
+def test_layer_forward_conv(dtype, mode):
+    """The forward-looking in-chunk convolution for the target (option conv_forward: tap j reads the token j
+    ahead, zero past the chunk's end), against the oracle; row 1 also packs two documents, which the forward
+    window (never leaving its chunk) does not see."""
+    eta = 0.05 if mode != "mse" else 0.5
+    cfg = small_cfg(dtype, mode, B=2, n=1536, d=264, f=392, C=256, eta=eta)
+    k = cfg.seq_len // cfg.chunk
+    starts = np.zeros((2, k), dtype=np.uint8)
+    starts[1, [0, 3]] = 1
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    O, Wf = cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"],
+                                      g["conv_w"], cfg.chunk, cfg.eta, mode,
+                                      doc_starts=torch.from_numpy(starts).cuda(), conv_forward=True)
+    torch.cuda.synchronize()
+    Oref, Wref = orc.inplace_layer(*(ti.to_f64(x[n]) for n in ("H", "X0", "W_gate", "W_up", "W_down0", "W_target",
+                                                                "conv_w")), cfg.chunk, cfg.eta,
+                                   "dot" if mode == "dot_scan" else mode, doc_starts=starts, conv_forward=True)
+    W0 = ti.to_f64(x["W_down0"])
+    tol = TOL[dtype]
+    for b in range(2):
         assert rel(f64(O[b]), Oref[b]) < tol, b
         assert rel(f64(Wf[b]), Wref[b]) < tol and rel(f64(Wf[b]) - W0, Wref[b] - W0) < tol, b
 

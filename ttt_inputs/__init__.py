@@ -54,6 +54,7 @@ class InplaceConfig:
     var_target: float | None = None  # default 1/d_model
     var_conv: float = 0.25
     docs: int = 1        # documents packed into each row, of equal length in chunks
+    conv_forward: bool = False   # forward-looking in-chunk convolution for the target
 
     @property
     def tokens(self) -> int:
@@ -136,6 +137,9 @@ WORKLOADS = {
     "inplace_bf16_32k": InplaceConfig("inplace_bf16_32k", 1, 32768, 2560, 9728, 1024, 0.01, "dot", "bf16", seed=1001),
     "inplace_bf16_128k": InplaceConfig("inplace_bf16_128k", 1, 131072, 2560, 9728, 4096, 0.01, "dot", "bf16", seed=1002),
     "inplace_bf16_128k_c512": InplaceConfig("inplace_bf16_128k_c512", 1, 131072, 2560, 9728, 512, 0.01, "dot", "bf16", seed=1002),
+    # the 128K layer with the forward-looking in-chunk convolution (next-token-style target)
+    "inplace_bf16_128k_ntp": InplaceConfig("inplace_bf16_128k_ntp", 1, 131072, 2560, 9728, 4096, 0.01, "dot", "bf16",
+                                           seed=1002, conv_forward=True),
     # the 128K row packing 8 documents of 16K tokens (4 chunks each)
     "inplace_bf16_128k_8docs": InplaceConfig("inplace_bf16_128k_8docs", 1, 131072, 2560, 9728, 4096, 0.01, "dot", "bf16",
                                              seed=1002, docs=8),
