@@ -190,7 +190,7 @@ def chunk_prefix_form(Z, Vhat, W0, chunk, eta):
 
 
 def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
-                  mode, max_chunks=None, x0_halo=None, doc_starts=None, conv_forward=False):
+                  mode, max_chunks=None, x0_halo=None, doc_starts=None, conv_forward=False, W_init=None):
     """The whole In-Place TTT layer, one document per batch row.
 
     H, X0 [B, n, d]; W_gate, W_up [f, d]; W_down0 [d, f]; W_target [d, d];
@@ -202,6 +202,11 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
     row: a document starts at every flagged chunk c > 0 (chunk 0 always starts
     one), where the state is reset to W_down0 and the convolution restarts
     with zeros before the chunk's first row (Method §3, document boundaries).
+
+    `W_init` [B, d, f], if given, is each row's state before its first chunk
+    (resuming a sequence: the previous call's W_final, with `x0_halo` its last
+    K-1 rows of X0); a document start flagged at chunk 0 still resets to
+    W_down0 and the convolution to zeros.
 
     `conv_forward` takes the forward-looking in-chunk convolution
     (forward_chunk_conv1d) for the target; it reads no row outside the chunk,
@@ -230,10 +235,12 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
         else:
             Xfull, off = X0[b], 0
         W = _f64(W_down0).copy()       # document boundary: reset to the pretrained state
+        if W_init is not None:
+            W = _f64(W_init[b]).copy()  # a resumed row continues from its state
         doc_row = 0                    # first row of the current document in Xfull (the halo serves the first)
         for c in range(n_chunks):
             s, e = c * chunk, min((c + 1) * chunk, n)
-            if c > 0 and doc_starts is not None and doc_starts[b][c]:
+            if (c > 0 or W_init is not None or x0_halo is not None) and doc_starts is not None and doc_starts[b][c]:
                 W = _f64(W_down0).copy()   # a packed document starts here
                 doc_row = s + off
             lo = max(doc_row, s + off - (K - 1))

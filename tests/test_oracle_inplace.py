@@ -495,3 +495,30 @@ def test_forward_conv_layer_is_causal_per_chunk_and_composes(mode):
         X0p[c * C:] += rng.standard_normal(X0p[c * C:].shape)
         Op, _ = orc.inplace_layer(H[None], X0p[None], Wg, Wu, W0, Wt, cw, C, 0.1, mode, conv_forward=True)
         np.testing.assert_array_equal(Op[0, : (c + 1) * C], O[0, : (c + 1) * C])
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_resume_rows_with_their_own_states(mode):
+    """Two rows resumed at a chunk boundary, each from its own state (W_init, the first call's W_final) and its
+    own last K-1 rows of X0 (x0_halo): the two calls equal the single call.  A document flagged at the resume
+    point ignores both and starts from W_down0 with zeros."""
+    rng = _rng(33)
+    B, n, C, d, f, K = 2, 24, 6, 4, 5, 4
+    H = rng.standard_normal((B, n, d))
+    X0 = rng.standard_normal((B, n, d))
+    _, _, Wg, Wu, W0, Wt, cw = _problem(rng, n, d, f, K)
+    O, Wf = orc.inplace_layer(H, X0, Wg, Wu, W0, Wt, cw, C, 0.1, mode)
+    s = 2 * C
+    O1, W1 = orc.inplace_layer(H[:, :s], X0[:, :s], Wg, Wu, W0, Wt, cw, C, 0.1, mode)
+    O2, W2 = orc.inplace_layer(H[:, s:], X0[:, s:], Wg, Wu, W0, Wt, cw, C, 0.1, mode, W_init=W1,
+                               x0_halo=X0[:, s - (K - 1): s])
+    np.testing.assert_allclose(np.concatenate([O1, O2], axis=1), O, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(W2, Wf, rtol=1e-12, atol=1e-12)
+    starts = np.zeros((B, (n - s) // C), dtype=bool)
+    starts[1, 0] = True
+    O3, W3 = orc.inplace_layer(H[:, s:], X0[:, s:], Wg, Wu, W0, Wt, cw, C, 0.1, mode, W_init=W1,
+                               x0_halo=X0[:, s - (K - 1): s], doc_starts=starts)
+    O4, W4 = orc.inplace_layer(H[1:, s:], X0[1:, s:], Wg, Wu, W0, Wt, cw, C, 0.1, mode)
+    np.testing.assert_array_equal(O3[0], O2[0])
+    np.testing.assert_allclose(O3[1], O4[0], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(W3[1], W4[0], rtol=1e-12, atol=1e-12)
