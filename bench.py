@@ -153,9 +153,22 @@ def bench_generic(cfg, steps, warmup):
         g = {k: v.cuda() for k, v in x.items()}
         flags = cfg.doc_starts()
         docs = None if flags is None else torch.from_numpy(flags).cuda()
-        call = lambda: cw.ttt_chunk_apply_update(g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"],
-                                                 g["W_target"], g["conv_w"], cfg.chunk, cfg.eta, cfg.mode,
-                                                 doc_starts=docs, conv_forward=cfg.conv_forward)
+        w = (g["W_gate"], g["W_up"], g["W_down0"], g["W_target"], g["conv_w"])
+        if cfg.pieces > 1:
+            # the sequence in equal pieces, each call resuming the previous one's state and conv halo
+            L, K = cfg.seq_len // cfg.pieces, cfg.conv_k
+            Hs = [g["H"][:, i * L:(i + 1) * L].contiguous() for i in range(cfg.pieces)]
+            Xs = [g["X0"][:, i * L:(i + 1) * L].contiguous() for i in range(cfg.pieces)]
+            halos = [None] + [g["X0"][:, i * L - (K - 1): i * L].contiguous() for i in range(1, cfg.pieces)]
+
+            def call():
+                Wf = None
+                for i in range(cfg.pieces):
+                    _, Wf = cw.ttt_chunk_apply_update(Hs[i], Xs[i], *w, cfg.chunk, cfg.eta, cfg.mode, W_init=Wf,
+                                                      x0_halo=halos[i])
+        else:
+            call = lambda: cw.ttt_chunk_apply_update(g["H"], g["X0"], *w, cfg.chunk, cfg.eta, cfg.mode,
+                                                     doc_starts=docs, conv_forward=cfg.conv_forward)
     for _ in range(warmup):
         call()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -264,8 +277,11 @@ def main():
             out["config"]["docs_per_row"] = cfg.docs
         if cfg.conv_forward:
             out["config"]["conv"] = "forward in-chunk"
+        if cfg.pieces > 1:
+            out["config"]["calls_per_sequence"] = cfg.pieces
 
-    if not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot" and cfg.docs == 1 and not cfg.conv_forward:
+    if (not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot" and cfg.docs == 1 and not cfg.conv_forward and
+            cfg.pieces == 1):
         wall, per, _ = bench_inplace_dot(cfg, args.steps, args.warmup)
         fl, by = kernel_flops(cfg), kernel_bytes(cfg, 2 if dtype == "bf16" else 4)
         kern = {}

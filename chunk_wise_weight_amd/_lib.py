@@ -27,7 +27,8 @@ class InplaceShape(ctypes.Structure):
 
 
 class LayerOptions(ctypes.Structure):
-    _fields_ = [("doc_starts", ctypes.c_void_p), ("conv_forward", ctypes.c_int)]
+    _fields_ = [("doc_starts", ctypes.c_void_p), ("conv_forward", ctypes.c_int), ("W_init", ctypes.c_void_p),
+                ("x0_halo", ctypes.c_void_p)]
 
 
 class LactShape(ctypes.Structure):
@@ -153,12 +154,14 @@ def _workspace(nbytes: int, device, workspace):
 
 
 def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk: int, eta: float, mode="dot",
-                           O=None, W_final=None, workspace=None, doc_starts=None, conv_forward=False):
+                           O=None, W_final=None, workspace=None, doc_starts=None, conv_forward=False, W_init=None,
+                           x0_halo=None):
     """The whole In-Place layer.  Returns (O [B, n, d], W_final [B, d, f] fp32).
 
     Options (ttt_chunk_apply_update_ex): doc_starts, a uint8 (or bool) device tensor [B, seq_len // chunk] whose
     nonzero entries mark the chunks that start a new document in their row; conv_forward, the forward-looking
-    in-chunk convolution for the target."""
+    in-chunk convolution for the target; W_init [B, d, f] fp32 and x0_halo [B, K-1, d] to resume rows from an
+    earlier call (its W_final and its last K-1 rows of X0)."""
     B, n, d = H.shape
     f = W_gate.shape[0]
     K = conv_w.shape[1]
@@ -174,7 +177,11 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
     _need(W_final, "W_final", (B, d, f), torch.float32, dev)
     nbytes = ttt_inplace_workspace_bytes(shape, dt, mode, True)
     ws = _workspace(nbytes, dev, workspace)
-    if doc_starts is None and not conv_forward:
+    if W_init is not None:
+        _need(W_init, "W_init", (B, d, f), torch.float32, dev)
+    if x0_halo is not None:
+        _need(x0_halo, "x0_halo", (B, K - 1, d), dt, dev)
+    if doc_starts is None and not conv_forward and W_init is None and x0_halo is None:
         _check(lib().ttt_chunk_apply_update(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
                                             _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
                                             _ptr(conv_w), _ptr(O), _ptr(W_final), _ptr(ws), nbytes, _stream(dev)),
@@ -184,8 +191,8 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
         if doc_starts.dtype == torch.bool:
             doc_starts = doc_starts.to(torch.uint8)
         _need(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), torch.uint8, dev)
-    opts = LayerOptions(ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None else None,
-                        1 if conv_forward else 0)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+    opts = LayerOptions(ptr(doc_starts), 1 if conv_forward else 0, ptr(W_init), ptr(x0_halo))
     _check(lib().ttt_chunk_apply_update_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
                                            _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
                                            _ptr(conv_w), ctypes.byref(opts), _ptr(O), _ptr(W_final), _ptr(ws),

@@ -29,6 +29,8 @@ struct Plan {
   size_t off_Y, off_WtT, off_Zt, off_Vt, off_Wc, off_dW, off_Wp, off_Tot, off_Rt, off_Wsh, total;
   const uint8_t* docs;  // document starts [B, k] (device) or null: one document per batch row
   bool conv_fwd;        // forward-looking in-chunk convolution for the target
+  const float* Winit;   // resumed rows: state before chunk 0 [B, d, f] fp32 (device) or null
+  const void* halo;     // resumed rows: X0 rows before the first token [B, K-1, d] (device) or null
 };
 
 int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
@@ -56,6 +58,8 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   if (mode != TTT_MODE_DOT && mode != TTT_MODE_MSE && mode != TTT_MODE_DOT_SCAN) return TTT_ERR_ARG;
   p->docs = nullptr;
   p->conv_fwd = false;
+  p->Winit = nullptr;
+  p->halo = nullptr;
   p->B = s->batch;
   p->n = s->seq_len;
   p->d = s->d_model;
@@ -106,11 +110,12 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
 
 inline int dev(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE; }
 
-// W_final[b] = W_down0 for every row (no chunks): the scan with zero chunks.
+// W_final[b] = W_down0 (a resumed row: its own state) for every row (no
+// chunks): the scan with zero chunks.
 template <typename T>
 int fill_initial_state(const Plan& p, const void* W0, float* Wf, hipStream_t s) {
   return dev(ttt::launch_chunk_scan<T>(nullptr, (const T*)W0, nullptr, Wf, (int)p.B, 0, (int64_t)p.d * p.f, 0.f, nullptr,
-                                       s));
+                                       p.Winit, s));
 }
 
 // Scale the target is produced with: the fused dot update takes eta folded
@@ -137,8 +142,13 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
     T* Rt = (T*)(ws + p.off_Rt);
     T* Wsh = p.esz == 2 ? (T*)(ws + p.off_Wsh) : nullptr;
     const T* Wcur = p.esz == 2 ? (const T*)Wsh : (const T*)(const void*)Wf;
+    if (p.Winit != nullptr) {      // resumed rows: the state and its operand copy start from W_init
+      int st = dev(ttt::launch_state_copy<T>(p.Winit, Wf, Wsh, B, df, s));
+      if (st != TTT_OK) return st;
+    }
     for (int c = 0; c < k; ++c) {
-      int st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, p.docs, B, n, d, f, C, c, eta, s));
+      int st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, p.docs, p.Winit != nullptr, B, n, d, f,
+                                            C, c, eta, s));
       if (st != TTT_OK) return st;
     }
     return TTT_OK;
@@ -147,11 +157,11 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
   int st;
   if (p.fused) {
     st = dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (T*)(ws + p.off_Wp), (float*)(ws + p.off_Tot),
-                                              B, n, d, f, C, p.S, p.docs, s));   // Vt carries eta
+                                              B, n, d, f, C, p.S, p.docs, p.Winit, s));   // Vt carries eta
   } else {
     float* dW = (float*)(ws + p.off_dW);
     st = dev(ttt::launch_chunk_delta<T>(Zt, Vt, dW, B, n, d, f, C, s));
-    if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, df, eta, p.docs, s));
+    if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, df, eta, p.docs, p.Winit, s));
   }
   if (st != TTT_OK) return st;
   return dev(ttt::launch_apply<T>(Zt, Wc, (int64_t)k * df, df, O, B, n, d, f, C, s));
@@ -168,7 +178,7 @@ int run_producers(const Plan& p, const void* H, const void* X0, const void* Wg, 
   T* WtT = (T*)(ws + p.off_WtT);
   int st = dev(ttt::launch_produce_z<T>((const T*)H, (const T*)Wg, (const T*)Wu, nullptr, Zt, rows, n, d, f, s));
   if (st == TTT_OK) st = dev(ttt::launch_conv<T>((const T*)X0, (const T*)cw, Y, rows, n, d, (int)p.K, p.docs, (int)p.C,
-                                                  p.conv_fwd, s));
+                                                  p.conv_fwd, (const T*)p.halo, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Wt, WtT, 1, d, d, 1.0f, s));
   if (st == TTT_OK) st = dev(ttt::launch_produce_vhat<T>(Y, WtT, Vt, rows, n, d, vscale, s));
   return st;
@@ -270,8 +280,13 @@ int ttt_chunk_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mod
   if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
   if (options != nullptr) {
     if (options->conv_forward != 0 && options->conv_forward != 1) return TTT_ERR_ARG;
+    if ((options->W_init != nullptr && !ok_ptr(options->W_init)) ||
+        (options->x0_halo != nullptr && !ok_ptr(options->x0_halo)))
+      return TTT_ERR_ARG;
     p.docs = options->doc_starts;
     p.conv_fwd = options->conv_forward == 1;
+    p.Winit = options->W_init;
+    p.halo = p.K > 1 ? options->x0_halo : nullptr;
   }
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -347,7 +362,7 @@ int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, float scale, con
   const int n = (int)p.n, d = (int)p.d, K = (int)p.K;
   if (dtype == TTT_BF16) {
     st = dev(ttt::launch_conv<bf16>((const bf16*)X0, (const bf16*)conv_w, (bf16*)(ws + p.off_Y), rows, n, d, K, nullptr,
-                                    (int)p.C, false, s));
+                                    (int)p.C, false, nullptr, s));
     if (st == TTT_OK)
       st = dev(ttt::launch_transpose<bf16>((const bf16*)W_target, (bf16*)(ws + p.off_WtT), 1, d, d, 1.0f, s));
     if (st == TTT_OK)
@@ -356,7 +371,7 @@ int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, float scale, con
     return st;
   }
   st = dev(ttt::launch_conv<float>((const float*)X0, (const float*)conv_w, (float*)(ws + p.off_Y), rows, n, d, K,
-                                   nullptr, (int)p.C, false, s));
+                                   nullptr, (int)p.C, false, nullptr, s));
   if (st == TTT_OK)
     st = dev(ttt::launch_transpose<float>((const float*)W_target, (float*)(ws + p.off_WtT), 1, d, d, 1.0f, s));
   if (st == TTT_OK)
@@ -392,9 +407,9 @@ int ttt_chunk_scan(const ttt_inplace_shape* shape, int dtype, float eta, const v
   const int64_t df = shape->d_model * shape->d_ff;
   if (dtype == TTT_BF16)
     return dev(ttt::launch_chunk_scan<bf16>(dW, (const bf16*)W_down0, (bf16*)Wc, W_final, (int)shape->batch, k, df,
-                                            eta, nullptr, s));
+                                            eta, nullptr, nullptr, s));
   return dev(ttt::launch_chunk_scan<float>(dW, (const float*)W_down0, (float*)Wc, W_final, (int)shape->batch, k, df,
-                                           eta, nullptr, s));
+                                           eta, nullptr, nullptr, s));
 }
 
 static size_t update_scan_ws(const ttt_inplace_shape* s, int dtype) {
@@ -430,9 +445,9 @@ int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void*
   if (n == 0) {
     if (dtype == TTT_BF16)
       return dev(ttt::launch_chunk_scan<bf16>(nullptr, (const bf16*)W_down0, nullptr, W_final, B, 0, df, 0.f, nullptr,
-                                                s));
+                                                nullptr, s));
     return dev(ttt::launch_chunk_scan<float>(nullptr, (const float*)W_down0, nullptr, W_final, B, 0, df, 0.f,
-                                                 nullptr, s));
+                                                 nullptr, nullptr, s));
   }
   if (!ok_ptr(Zt) || !ok_ptr(Vt) || !ok_ptr(Wc)) return TTT_ERR_ARG;
   const size_t need = update_scan_ws(shape, dtype);
@@ -444,10 +459,11 @@ int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void*
   float* Tot = S > 1 ? (float*)(ws + align_up((size_t)B * (k - k / S) * df * esz)) : nullptr;
   if (dtype == TTT_BF16)
     return dev(ttt::launch_chunk_update_scan<bf16>((const bf16*)Zt, (const bf16*)Vt, (const bf16*)W_down0, (bf16*)Wc,
-                                                   W_final, (bf16*)Wp, Tot, B, n, d, f, C, S, nullptr, s));
+                                                   W_final, (bf16*)Wp, Tot, B, n, d, f, C, S, nullptr,
+                                                   nullptr, s));
   return dev(ttt::launch_chunk_update_scan<float>((const float*)Zt, (const float*)Vt, (const float*)W_down0,
                                                   (float*)Wc, W_final, (float*)Wp, Tot, B, n, d, f, C, S, nullptr,
-                                                  s));
+                                                  nullptr, s));
 }
 
 int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Zt, const void* Wc, void* O, void* stream) {

@@ -13,11 +13,14 @@
 namespace ttt {
 
 // Packed documents: docs [B, k] (may be null) flags the chunks that start a new
-// document in their batch row; chunk 0 always starts one.  At a document start
-// the state starts again from W_down0 and the convolution from zeros, so that
+// document in their batch row; chunk 0 always starts one unless the call
+// resumes its rows (cont), when only a flag does.  At a document start the
+// state starts again from W_down0 and the convolution from zeros, so that
 // nothing of the previous document reaches it (Method §3, document boundaries).
-__device__ __forceinline__ bool doc_start(const uint8_t* __restrict__ docs, int64_t b, int k, int c) {
-  return c == 0 || (docs != nullptr && docs[b * k + c] != 0);
+__device__ __forceinline__ bool doc_start(const uint8_t* __restrict__ docs, int64_t b, int k, int c,
+                                          bool cont = false) {
+  if (c == 0 && !cont) return true;
+  return docs != nullptr && docs[b * k + c] != 0;
 }
 
 
@@ -36,7 +39,8 @@ constexpr int kConvRows = 8;
 // next-token example, Method §2); else tap KW - 1 is the current token.
 template <typename T, int KW, bool FWD>
 __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T* __restrict__ cw, T* __restrict__ Y,
-                                              int64_t rows, int n, int d, const uint8_t* __restrict__ docs, int C_) {
+                                              int64_t rows, int n, int d, const uint8_t* __restrict__ docs, int C_,
+                                              const T* __restrict__ halo) {
   constexpr int V = Vec<T>::V, RW = kConvRows, NIN = RW + KW - 1;
   const int nchunk = d / V;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -48,6 +52,10 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
   // in one chunk (C_ % 8 == 0)
   const int lo = doc_start(docs, r0 / n, n / C_, pos0 / C_) ? (pos0 / C_) * C_ : 0;
   const int hi = (pos0 / C_ + 1) * C_;
+  // a resumed row reads the previous call's last KW - 1 rows (halo [B, KW - 1, d])
+  // before its first token, unless a document starts there
+  const bool use_halo = !FWD && halo != nullptr && pos0 == 0 && !doc_start(docs, r0 / n, n / C_, 0, true);
+  const T* hrow = use_halo ? halo + ((r0 / n) * (KW - 1)) * (int64_t)d + ch : nullptr;
   float w[V][KW];
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(cw + (int64_t)ch * KW);
@@ -71,7 +79,9 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
 #pragma unroll
   for (int i = 0; i < NIN; ++i) {
     const bool live = FWD ? (i < RW || pos0 + i < hi) : (i >= KW - 1 || pos0 + i - (KW - 1) >= lo);
-    in[i] = live ? *reinterpret_cast<const u32x4*>(base + (int64_t)i * d) : u32x4{0u, 0u, 0u, 0u};
+    if (live) in[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)i * d);
+    else if (use_halo && i < KW - 1) in[i] = *reinterpret_cast<const u32x4*>(hrow + (int64_t)i * d);
+    else in[i] = u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
@@ -350,22 +360,28 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_delta(const T* __restrict__ Zt, const T* __re
 template <typename T>
 __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW, const T* __restrict__ W0,
                                                     T* __restrict__ Wc, float* __restrict__ Wf, int k, int64_t df,
-                                                    float eta, const uint8_t* __restrict__ docs) {
+                                                    float eta, const uint8_t* __restrict__ docs,
+                                                    const float* __restrict__ Winit) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   const int b = blockIdx.y;
   if (e >= df) return;
   const f32x4 w0 = load4(W0 + e);
+  // a resumed row (Winit) starts from its own state unless a document starts at chunk 0
+  f32x4 base = (Winit != nullptr && !(k > 0 && doc_start(docs, b, k, 0, true))) ? load4(Winit + b * df + e) : w0;
   f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f};
   const float* src = dW + (int64_t)b * k * df + e;
   T* dst = Wc + (int64_t)b * k * df + e;
   for (int c = 0; c < k; ++c) {
-    if (doc_start(docs, b, k, c)) s = (f32x4){0.f, 0.f, 0.f, 0.f};
-    store4(dst + (int64_t)c * df, fmaf(eta, s[0], w0[0]), fmaf(eta, s[1], w0[1]), fmaf(eta, s[2], w0[2]),
-           fmaf(eta, s[3], w0[3]));
+    if (c > 0 && doc_start(docs, b, k, c)) {
+      s = (f32x4){0.f, 0.f, 0.f, 0.f};
+      base = w0;
+    }
+    store4(dst + (int64_t)c * df, fmaf(eta, s[0], base[0]), fmaf(eta, s[1], base[1]), fmaf(eta, s[2], base[2]),
+           fmaf(eta, s[3], base[3]));
     s += load4(src + (int64_t)c * df);
   }
-  store4(Wf + (int64_t)b * df + e, fmaf(eta, s[0], w0[0]), fmaf(eta, s[1], w0[1]), fmaf(eta, s[2], w0[2]),
-         fmaf(eta, s[3], w0[3]));
+  store4(Wf + (int64_t)b * df + e, fmaf(eta, s[0], base[0]), fmaf(eta, s[1], base[1]), fmaf(eta, s[2], base[2]),
+         fmaf(eta, s[3], base[3]));
 }
 
 // Fused delta + scan.  The per-chunk delta does not depend on the state, so
@@ -418,7 +434,8 @@ template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T* __restrict__ Vt,
                                                const T* __restrict__ W0, T* __restrict__ Wc, T* __restrict__ Wp,
                                                float* __restrict__ Tot, float* __restrict__ Wf, int n, int d, int f,
-                                               int C_, int S, const uint8_t* __restrict__ docs) {
+                                               int C_, int S, const uint8_t* __restrict__ docs,
+                                               const float* __restrict__ Winit) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (f + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
@@ -446,12 +463,14 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
   zero_acc<G>(acc);
   T* wc = Wc + (int64_t)b * k * df;
   if (sg == 0) {
+    // a resumed row (Winit) starts from its own fp32 state unless a document starts at chunk 0
+    const float* wi = (Winit != nullptr && !doc_start(docs, b, k, 0, true)) ? Winit + (int64_t)b * df : nullptr;
     for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
-      const f32x4 w = load4(W0 + ro + dj);
+      const f32x4 w = wi != nullptr ? load4(wi + ro + dj) : load4(W0 + ro + dj);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
     });
-    stage_state<G, G::Smem>(acc, wc, smem, j0, i0, d, f);                // chunk 0: W_down0
+    stage_state<G, G::Smem>(acc, wc, smem, j0, i0, d, f);                // chunk 0: W_down0 (or the resumed state)
   } else if (docs != nullptr && docs[(int64_t)b * k + c0] != 0) {
     // a document starts with this segment: its states are absolute from the start (the fix-up writes chunk c0's)
     for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
@@ -575,7 +594,7 @@ template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __restrict__ W0,
                                        const T* __restrict__ Wcur, T* __restrict__ O, const T* __restrict__ Vt,
                                        T* __restrict__ Rt, const uint8_t* __restrict__ docs, int n, int d, int f,
-                                       int C_, int c, float rscale) {
+                                       int C_, int c, float rscale, bool cont) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
@@ -591,7 +610,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
   DmaOp<G::NW, G::BP> op;
   DmaOpMN<T, G::NW, G::BQ> oq;
   // the state chunk c is applied with: W_down0 (shared) where a document starts, else this row's state copy
-  const T* W = doc_start(docs, b, n / C_, c) ? W0 : Wcur + (int64_t)b * d * f;
+  const T* W = doc_start(docs, b, n / C_, c, cont) ? W0 : Wcur + (int64_t)b * d * f;
   op.init(W + (int64_t)i0 * f, nullptr, min(G::BP, d - i0), ldb, (unsigned)ldb);
   oq.init(Zt + (int64_t)b * f * n + (int64_t)c * C_ + t0, min(G::BQ, C_ - t0), (uint64_t)n * esz<T>(), f);
   typename G::Frag acc[G::NPB][G::NQB];
@@ -677,7 +696,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __restrict__ Rt, const T* __restrict__ W0,
                                         float* __restrict__ Ws, T* __restrict__ Wsh, const uint8_t* __restrict__ docs,
-                                        int n, int d, int f, int C_, int c) {
+                                        int n, int d, int f, int C_, int c, bool cont) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (f + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
@@ -697,7 +716,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __res
   float* ws = Ws + (int64_t)b * d * f;
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);                       // entries outside the state stay zero (never stored)
-  const bool fresh = doc_start(docs, b, n / C_, c);
+  const bool fresh = doc_start(docs, b, n / C_, c, cont);
   for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
     const f32x4 w = fresh ? load4(W0 + ro + dj) : load4_stream(ws + ro + dj);
 #pragma unroll
@@ -718,15 +737,15 @@ static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 template <typename T>
 hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, const uint8_t* docs, int C,
-                       bool fwd, hipStream_t s) {
+                       bool fwd, const T* halo, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   const int64_t threads = (rows / kConvRows) * (d / Vec<T>::V);     // rows % kConvRows == 0 (n % 8 == 0)
   const dim3 g((unsigned)cdiv(threads, 256));
   switch (K) {
 #define TTT_KW(KW)                                                                                            \
   case KW:                                                                                                    \
-    if (fwd) k_conv<T, KW, true><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d, docs, C);                         \
-    else k_conv<T, KW, false><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d, docs, C);                            \
+    if (fwd) k_conv<T, KW, true><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d, docs, C, halo);                   \
+    else k_conv<T, KW, false><<<g, 256, 0, s>>>(X0, cw, Y, rows, n, d, docs, C, halo);                      \
     break;
     TTT_KW(1) TTT_KW(2) TTT_KW(3) TTT_KW(4) TTT_KW(5) TTT_KW(6) TTT_KW(7) TTT_KW(8)
 #undef TTT_KW
@@ -768,18 +787,21 @@ hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n,
 
 template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
-                             const uint8_t* docs, hipStream_t s) {
+                             const uint8_t* docs, const float* Winit, hipStream_t s) {
   if (B == 0) return hipSuccess;
-  k_chunk_scan<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(dW, W0, Wc, Wf, k, df, eta, docs);
+  k_chunk_scan<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(dW, W0, Wc, Wf, k, df, eta, docs,
+                                                                                 Winit);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
-                                    int B, int n, int d, int f, int Cs, int S, const uint8_t* docs, hipStream_t s) {
+                                    int B, int n, int d, int f, int Cs, int S, const uint8_t* docs,
+                                    const float* Winit, hipStream_t s) {
   const int64_t tiles = cdiv(f, kWB) * cdiv(d, kWB) * B * S;
   if (tiles == 0) return hipSuccess;
-  k_chunk_update_scan<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f, Cs, S, docs);
+  k_chunk_update_scan<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f, Cs, S, docs,
+                                                             Winit);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t df = (int64_t)d * f;
@@ -799,33 +821,55 @@ hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O,
 
 template <typename T>
 hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
-                            T* Rt, const uint8_t* docs, int B, int n, int d, int f, int Cs, int c, float eta,
-                            hipStream_t s) {
+                            T* Rt, const uint8_t* docs, bool cont, int B, int n, int d, int f, int Cs, int c,
+                            float eta, hipStream_t s) {
   k_mse_apply<T><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, docs, n, d,
-                                                                              f, Cs, c, -eta / (float)Cs);
+                                                                              f, Cs, c, -eta / (float)Cs, cont);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, docs, n, d, f,
-                                                                               Cs, c);
+                                                                               Cs, c, cont);
+  return hipGetLastError();
+}
+
+// The states a resumed MSE scan starts from: Wf[b] = Winit[b] (fp32) and, for
+// a dtype operand, Wsh[b] its rounded copy for the first apply.
+template <typename T>
+__global__ __launch_bounds__(256) void k_state_copy(const float* __restrict__ Winit, float* __restrict__ Wf,
+                                                    T* __restrict__ Wsh, int64_t df) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= df) return;
+  const int64_t o = (int64_t)blockIdx.y * df + e;
+  const f32x4 w = load4(Winit + o);
+  store4(Wf + o, w[0], w[1], w[2], w[3]);
+  if (Wsh != nullptr) store4(Wsh + o, w[0], w[1], w[2], w[3]);
+}
+
+template <typename T>
+hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64_t df, hipStream_t s) {
+  if (B == 0 || df == 0) return hipSuccess;
+  k_state_copy<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(Winit, Wf, Wsh, df);
   return hipGetLastError();
 }
 
 #define TTT_INST(T)                                                                                               \
   template hipError_t launch_conv<T>(const T*, const T*, T*, int64_t, int, int, int, const uint8_t*, int, bool,  \
-                                     hipStream_t);                                                                \
+                                     const T*, hipStream_t);                                                      \
   template hipError_t launch_transpose<T>(const T*, T*, int, int, int, float, hipStream_t);                      \
   template hipError_t launch_produce_z<T>(const T*, const T*, const T*, T*, T*, int64_t, int, int, int,          \
                                           hipStream_t);                                                           \
   template hipError_t launch_produce_vhat<T>(const T*, const T*, T*, int64_t, int, int, float, hipStream_t);     \
   template hipError_t launch_chunk_delta<T>(const T*, const T*, float*, int, int, int, int, int, hipStream_t);   \
   template hipError_t launch_chunk_scan<T>(const float*, const T*, T*, float*, int, int, int64_t, float,         \
-                                           const uint8_t*, hipStream_t);                                          \
+                                           const uint8_t*, const float*, hipStream_t);                            \
   template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, T*, float*, int,      \
-                                                  int, int, int, int, int, const uint8_t*, hipStream_t);          \
+                                                  int, int, int, int, int, const uint8_t*, const float*,          \
+                                                  hipStream_t);                                                   \
   template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int,          \
                                       hipStream_t);                                                               \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
-                                          const uint8_t*, int, int, int, int, int, int, float, hipStream_t);
+                                          const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t); \
+  template hipError_t launch_state_copy<T>(const float*, float*, T*, int, int64_t, hipStream_t);
 TTT_INST(float)
 TTT_INST(bf16)
 #undef TTT_INST

@@ -10,7 +10,7 @@ typedef __bf16 bf16;
 
 template <typename T>
 hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, const uint8_t* docs, int C,
-                       bool fwd, hipStream_t s);
+                       bool fwd, const T* halo, hipStream_t s);
 template <typename T>
 hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int C, float scale, hipStream_t s);
 template <typename T>
@@ -23,10 +23,11 @@ template <typename T>
 hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n, int d, int f, int C, hipStream_t s);
 template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
-                             const uint8_t* docs, hipStream_t s);
+                             const uint8_t* docs, const float* Winit, hipStream_t s);
 template <typename T>
 hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
-                                    int B, int n, int d, int f, int C, int S, const uint8_t* docs, hipStream_t s);
+                                    int B, int n, int d, int f, int C, int S, const uint8_t* docs, const float* Winit,
+                                    hipStream_t s);
 
 // Number of sequence segments the fused update-scan runs side by side (a
 // segment count divides the chunk count), by a two-term cost model: the K loop
@@ -56,8 +57,10 @@ hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O,
                         hipStream_t s);
 template <typename T>
 hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
-                            T* Rt, const uint8_t* docs, int B, int n, int d, int f, int C, int c, float eta,
-                            hipStream_t s);
+                            T* Rt, const uint8_t* docs, bool cont, int B, int n, int d, int f, int C, int c,
+                            float eta, hipStream_t s);
+template <typename T>
+hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64_t df, hipStream_t s);
 
 // LaCT SwiGLU fast weight (one call runs every chunk of every (batch, head)).
 struct LactArgs {

@@ -137,7 +137,8 @@ typedef struct {
    * c is applied with W_down0 and updates it) and the convolution restarts:
    * rows before the chunk's first token read as zero.  W_final is the state
    * after the row's last chunk, i.e. the last document's.  Read on the
-   * device; any byte value is valid.  NULL: one document per row. */
+   * device; any byte value is valid.  NULL: one document per row.  (Entry 0
+   * matters only for resumed rows, below.) */
   const unsigned char* doc_starts;
   /* 0: the causal convolution of ttt_chunk_apply_update.  1: the forward-
    * looking in-chunk reading of the review's next-token example (Method §2):
@@ -147,6 +148,18 @@ typedef struct {
    * conv_w[:, 1] = 1 the target of a token is the next token (zero at a
    * chunk's last token).  Other values: TTT_ERR_ARG. */
   int conv_forward;
+  /* Resuming rows that continue a sequence from an earlier call (e.g. a long
+   * document processed in pieces): W_init [B, d, f] fp32 (DEVICE, 16-byte
+   * aligned) is each row's state before chunk 0 -- the earlier call's
+   * W_final -- and x0_halo [B, K-1, d] dtype (DEVICE, 16-byte aligned) holds
+   * the K-1 rows of X0 before the first token, which the causal convolution
+   * reads instead of zeros.  Either may be NULL (W_down0, resp. zeros).  With
+   * either given, chunk 0 starts a new document only where doc_starts flags
+   * it (then W_down0 and zeros, as at any document start).  Two calls on the
+   * halves of a sequence, the second resumed this way, give the single call's
+   * results up to rounding order. */
+  const float* W_init;
+  const void* x0_halo;
 } ttt_layer_options;
 
 /* The layer of ttt_chunk_apply_update with options (above); same arguments,

@@ -281,6 +281,40 @@ def test_layer_forward_conv(dtype, mode):
         assert rel(f64(Wf[b]), Wref[b]) < tol and rel(f64(Wf[b]) - W0, Wref[b] - W0) < tol, b
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["dot", "dot_scan", "mse"])
+def test_layer_resumed_in_two_calls(dtype, mode):
+    """A sequence processed in two calls, the second resuming each row from the first call's W_final (W_init)
+    and its last K-1 rows of X0 (x0_halo), against the oracle's single call over the whole sequence.  The second
+    call (4 chunks, so the fused dot plan runs sequence segments) flags a document start at its first chunk in
+    row 1, which ignores both and matches a single call with a document starting there."""
+    eta = 0.05 if mode != "mse" else 0.5
+    cfg = small_cfg(dtype, mode, B=2, n=1536, d=264, f=392, C=256, eta=eta)
+    C, K = cfg.chunk, cfg.conv_k
+    s = 2 * C
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    w = (g["W_gate"], g["W_up"], g["W_down0"], g["W_target"], g["conv_w"])
+    O1, W1 = cw.ttt_chunk_apply_update(g["H"][:, :s].contiguous(), g["X0"][:, :s].contiguous(), *w, C, cfg.eta, mode)
+    starts = torch.zeros(2, (cfg.seq_len - s) // C, dtype=torch.uint8, device="cuda")
+    starts[1, 0] = 1
+    O2, W2 = cw.ttt_chunk_apply_update(g["H"][:, s:].contiguous(), g["X0"][:, s:].contiguous(), *w, C, cfg.eta,
+                                       mode, W_init=W1, x0_halo=g["X0"][:, s - (K - 1): s].contiguous(),
+                                       doc_starts=starts)
+    torch.cuda.synchronize()
+    full = np.zeros((2, cfg.seq_len // C), dtype=np.uint8)
+    full[1, s // C] = 1
+    Oref, Wref = orc.inplace_layer(*(ti.to_f64(x[n]) for n in ("H", "X0", "W_gate", "W_up", "W_down0", "W_target",
+                                                                "conv_w")), C, cfg.eta,
+                                   "dot" if mode == "dot_scan" else mode, doc_starts=full)
+    O = torch.cat([O1, O2], dim=1)
+    W0 = ti.to_f64(x["W_down0"])
+    tol = TOL[dtype]
+    for b in range(2):
+        assert rel(f64(O[b]), Oref[b]) < tol, b
+        assert rel(f64(W2[b]), Wref[b]) < tol and rel(f64(W2[b]) - W0, Wref[b] - W0) < tol, b
+
+
 def test_layer_bf16_chunk_not_multiple_of_kstep():
     # chunk 40: the dot plan falls back to materialised deltas + scan
     cfg = small_cfg("bf16", "dot", B=1, n=400, d=128, f=256, C=40, eta=0.02)

@@ -55,6 +55,7 @@ class InplaceConfig:
     var_conv: float = 0.25
     docs: int = 1        # documents packed into each row, of equal length in chunks
     conv_forward: bool = False   # forward-looking in-chunk convolution for the target
+    pieces: int = 1      # the sequence processed in this many calls, each resuming the previous one
 
     @property
     def tokens(self) -> int:
@@ -140,6 +141,9 @@ WORKLOADS = {
     # the 128K layer with the forward-looking in-chunk convolution (next-token-style target)
     "inplace_bf16_128k_ntp": InplaceConfig("inplace_bf16_128k_ntp", 1, 131072, 2560, 9728, 4096, 0.01, "dot", "bf16",
                                            seed=1002, conv_forward=True),
+    # the 128K layer processed as 4 calls of 32K tokens, each resuming the previous one's state and conv halo
+    "inplace_bf16_128k_4pieces": InplaceConfig("inplace_bf16_128k_4pieces", 1, 131072, 2560, 9728, 4096, 0.01, "dot",
+                                               "bf16", seed=1002, pieces=4),
     # the 128K row packing 8 documents of 16K tokens (4 chunks each)
     "inplace_bf16_128k_8docs": InplaceConfig("inplace_bf16_128k_8docs", 1, 131072, 2560, 9728, 4096, 0.01, "dot", "bf16",
                                              seed=1002, docs=8),
