@@ -11,9 +11,19 @@ Sources: "Test-Time Training Done Right" review --
 "ViT^3" review, Insight 2 and 3: one full-batch GD step per chunk, eta = 1.
 
 Readings: the per-token loss is (1/2)||f_W(k_i) - v_i||^2, summed (no mean)
-over the chunk; scalar eta; plain simultaneous GD on W1, W3, W2 (no weight
-normalisation, no Muon); layout q, k, v [B, H, n, dh], W1, W3 [H, m, dh],
-W2 [H, dh, m], every (batch row, head) with its own state.
+over the chunk; scalar eta; plain simultaneous GD on W1, W3, W2; layout
+q, k, v [B, H, n, dh], W1, W3 [H, m, dh], W2 [H, dh, m], every (batch row,
+head) with its own state.
+
+Variants (LaCT Model Architecture §1, eq. (3) and the dot-product loss; §2,
+fast-weight normalisation), each off by default:
+  * per-token learning rates eta_i weighting each token's loss inside the
+    gradient (eq. (3)), on top of the scalar eta;
+  * the dot-product loss L = -f_W(k)^T v, whose gradient with respect to the
+    output is -v in place of the residual f_W(k) - v;
+  * L2 weight normalisation after each update, along each matrix's input
+    dimension: every row of W1, W3 (over d_h) and of W2 (over the hidden
+    width) is scaled to unit norm.  Muon is not provided.
 """
 from __future__ import annotations
 
@@ -21,7 +31,7 @@ import numpy as np
 
 from .inplace import silu
 
-__all__ = ["swiglu_apply", "swiglu_loss", "swiglu_grads", "lact_layer"]
+__all__ = ["swiglu_apply", "swiglu_loss", "swiglu_grads", "l2_normalize_rows", "lact_layer"]
 
 
 def _f64(a):
@@ -40,9 +50,11 @@ def swiglu_loss(kc, vc, W1, W3, W2):
     return float(0.5 * np.sum(R * R))
 
 
-def swiglu_grads(kc, vc, W1, W3, W2):
-    """Gradients (G1, G3, G2) of swiglu_loss with respect to W1, W3, W2,
-    by the chain rule written out by hand."""
+def swiglu_grads(kc, vc, W1, W3, W2, eta_tok=None, loss="mse"):
+    """Gradients (G1, G3, G2) of the chunk loss with respect to W1, W3, W2, by
+    the chain rule written out by hand: swiglu_loss ("mse") or the dot-product
+    loss sum_i -f_W(k_i)^T v_i ("dot"), each token's term weighted by
+    eta_tok[i] when given (eq. (3))."""
     kc, vc, W1, W3, W2 = map(_f64, (kc, vc, W1, W3, W2))
     A = kc @ W1.T                     # [C, m]
     U = kc @ W3.T                     # [C, m]
@@ -50,7 +62,14 @@ def swiglu_grads(kc, vc, W1, W3, W2):
         sig = 1.0 / (1.0 + np.exp(-A))
     S = A * sig                       # silu(A)
     Hh = S * U                        # hidden [C, m]
-    R = Hh @ W2.T - vc                # residual [C, dh]
+    if loss == "mse":
+        R = Hh @ W2.T - vc            # d loss / d output: the residual [C, dh]
+    elif loss == "dot":
+        R = -vc                       # d(-f^T v) / d f
+    else:
+        raise ValueError(f"unknown loss {loss!r}")
+    if eta_tok is not None:
+        R = R * _f64(eta_tok)[:, None]   # per-token learning rates weight each token's term
     G2 = R.T @ Hh                     # [dh, m]
     dH = R @ W2                       # [C, m]
     dU = dH * S
@@ -60,7 +79,15 @@ def swiglu_grads(kc, vc, W1, W3, W2):
     return G1, G3, G2
 
 
-def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply", update_mask=None):
+def l2_normalize_rows(W):
+    """Each row of W scaled to unit L2 norm (the fast-weight normalisation of
+    LaCT Model Architecture §2, along the input dimension of W [out, in])."""
+    W = _f64(W)
+    return W / np.linalg.norm(W, axis=-1, keepdims=True)
+
+
+def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply", update_mask=None, eta_tok=None,
+               loss="mse", weight_norm=False):
     """LaCT layer over chunks.  q, k, v [B, H, n, dh]; W1, W3 [H, m, dh];
     W2 [H, dh, m].  Returns (O [B, H, n, dh], W1_f, W3_f [B, H, m, dh],
     W2_f [B, H, dh, m]).
@@ -69,7 +96,11 @@ def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply", updat
     on the flagged chunks only; every chunk is applied.  With update-then-apply
     this is the strided block-wise causal mask of the review's section on the
     order of the apply and update operations (its video use updates on the
-    clean chunks only)."""
+    clean chunks only).
+
+    `eta_tok` [B, H, n] gives per-token learning rates, `loss` is "mse" or
+    "dot", and `weight_norm` L2-normalises the rows of each matrix after every
+    update (see the module notes)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
     B, Hn, n, dh = q.shape
@@ -85,8 +116,11 @@ def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply", updat
                 if order == "apply_then_update":
                     O[b, h, r] = swiglu_apply(q[b, h, r], w1, w3, w2)
                 if update_mask is None or update_mask[c]:
-                    g1, g3, g2 = swiglu_grads(k[b, h, r], v[b, h, r], w1, w3, w2)
+                    et = None if eta_tok is None else _f64(eta_tok)[b, h, r]
+                    g1, g3, g2 = swiglu_grads(k[b, h, r], v[b, h, r], w1, w3, w2, et, loss)
                     w1, w3, w2 = w1 - eta * g1, w3 - eta * g3, w2 - eta * g2
+                    if weight_norm:
+                        w1, w3, w2 = l2_normalize_rows(w1), l2_normalize_rows(w3), l2_normalize_rows(w2)
                 if order == "update_then_apply":
                     O[b, h, r] = swiglu_apply(q[b, h, r], w1, w3, w2)
                 elif order != "apply_then_update":

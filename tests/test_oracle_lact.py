@@ -169,3 +169,51 @@ def test_update_mask_composes_from_unmasked_runs(order):
     np.testing.assert_allclose(O[..., r2, :], O2, rtol=1e-12, atol=1e-14)
     for got, want in ((W1f, b1), (W3f, b3), (W2f, b2)):
         np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("loss", ["mse", "dot"])
+def test_token_rates_and_losses_match_autograd(loss):
+    """One chunk spanning the sequence: the step on sum_i eta_i L_i (eq. (3)), with the squared error or the
+    dot-product loss -f(k)^T v, equals torch autograd's; the queries then see the stepped weights."""
+    q, k, v, W1, W3, W2 = _problem(13, H=1, n=10)
+    eta = 0.4
+    et = np.random.default_rng(14).uniform(0.2, 1.5, size=(1, 1, 10))
+    O, W1f, W3f, W2f = orc.lact_layer(q, k, v, W1, W3, W2, 10, eta, "update_then_apply", eta_tok=et, loss=loss)
+    w1, w3, w2 = (torch.from_numpy(a[0].copy()).requires_grad_(True) for a in (W1, W3, W2))
+    y = _torch_swiglu(torch.from_numpy(k[0, 0]), w1, w3, w2)
+    vt, e = torch.from_numpy(v[0, 0]), torch.from_numpy(et[0, 0])
+    per_tok = 0.5 * ((y - vt) ** 2).sum(dim=1) if loss == "mse" else -(y * vt).sum(dim=1)
+    (e * per_tok).sum().backward()
+    n1, n3, n2 = (w.detach() - eta * w.grad for w in (w1, w3, w2))
+    for got, want in ((W1f[0, 0], n1), (W3f[0, 0], n3), (W2f[0, 0], n2)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-11, atol=1e-13)
+    ref = _torch_swiglu(torch.from_numpy(q[0, 0]), n1, n3, n2).numpy()
+    np.testing.assert_allclose(O[0, 0], ref, rtol=1e-11, atol=1e-13)
+
+
+def test_constant_token_rate_is_a_scaled_eta():
+    q, k, v, W1, W3, W2 = _problem(15)
+    a = orc.lact_layer(q, k, v, W1, W3, W2, 4, 0.5, eta_tok=np.full(q.shape[:3], 0.3))
+    b = orc.lact_layer(q, k, v, W1, W3, W2, 4, 0.15)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-12, atol=1e-14)
+
+
+def test_weight_norm_matches_torch_normalize():
+    """LaCT Model Architecture §2: after the step, every row of each matrix (its input dimension) is scaled to
+    unit L2 norm -- torch's F.normalize of the autograd step on one chunk; after several chunks every row still
+    has unit norm."""
+    q, k, v, W1, W3, W2 = _problem(16, H=1, n=10)
+    eta = 0.8
+    O, W1f, W3f, W2f = orc.lact_layer(q, k, v, W1, W3, W2, 10, eta, weight_norm=True)
+    w1, w3, w2 = (torch.from_numpy(a[0].copy()).requires_grad_(True) for a in (W1, W3, W2))
+    (0.5 * ((_torch_swiglu(torch.from_numpy(k[0, 0]), w1, w3, w2) - torch.from_numpy(v[0, 0])) ** 2).sum()).backward()
+    n1, n3, n2 = (F.normalize(w.detach() - eta * w.grad, dim=-1) for w in (w1, w3, w2))
+    for got, want in ((W1f[0, 0], n1), (W3f[0, 0], n3), (W2f[0, 0], n2)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(O[0, 0], _torch_swiglu(torch.from_numpy(q[0, 0]), n1, n3, n2).numpy(), rtol=1e-11,
+                               atol=1e-13)
+    q, k, v, W1, W3, W2 = _problem(17)
+    _, W1f, W3f, W2f = orc.lact_layer(q, k, v, W1, W3, W2, 3, eta, weight_norm=True)
+    for W in (W1f, W3f, W2f):
+        np.testing.assert_allclose(np.linalg.norm(W, axis=-1), 1.0, rtol=1e-12)
