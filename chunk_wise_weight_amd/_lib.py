@@ -31,6 +31,11 @@ class LayerOptions(ctypes.Structure):
                 ("x0_halo", ctypes.c_void_p)]
 
 
+class LactOptions(ctypes.Structure):
+    _fields_ = [("order", ctypes.c_int), ("update_mask", ctypes.c_void_p), ("eta_tok", ctypes.c_void_p),
+                ("loss", ctypes.c_int), ("weight_norm", ctypes.c_int)]
+
+
 class LactShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("batch", "heads", "seq_len", "head_dim", "hidden", "chunk")]
 
@@ -64,8 +69,8 @@ _SIGNATURES = {
     "ttt_lact_workspace_bytes": (_I, [ctypes.POINTER(LactShape), _I, ctypes.POINTER(_S)]),
     "ttt_lact_swiglu": (_I, [ctypes.POINTER(LactShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                              _S, _P]),
-    "ttt_lact_swiglu_masked": (_I, [ctypes.POINTER(LactShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                    _P, _P, _S, _P]),
+    "ttt_lact_swiglu_ex": (_I, [ctypes.POINTER(LactShape), _I, _F, _P, _P, _P, _P, _P, _P,
+                                ctypes.POINTER(LactOptions), _P, _P, _P, _P, _P, _S, _P]),
 }
 
 _lib = None
@@ -357,11 +362,12 @@ def ttt_lact_workspace_bytes(shape: LactShape, dtype: torch.dtype) -> int:
 
 
 def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_then_apply", O=None, finals=None,
-                    workspace=None, update_mask=None):
+                    workspace=None, update_mask=None, eta_tok=None, loss="mse", weight_norm=False):
     """LaCT SwiGLU layer.  Returns (O [B, H, n, dh], W1_f, W3_f [B, H, m, dh], W2_f [B, H, dh, m]).
 
-    update_mask: optional host sequence of n // chunk flags; only the flagged chunks take the update step
-    (ttt_lact_swiglu_masked), every chunk is applied."""
+    Options (ttt_lact_swiglu_ex): update_mask, a host sequence of n // chunk flags (only the flagged chunks
+    take the update step, every chunk is applied); eta_tok, per-token learning rates [B, H, n] fp32 on the
+    device; loss, "mse" or "dot"; weight_norm, L2-normalise the weight rows after every update."""
     B, Hh, n, dh = q.shape
     m = W1.shape[1]
     dt, dev = q.dtype, q.device
@@ -382,17 +388,27 @@ def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_t
     nbytes = ttt_lact_workspace_bytes(shape, dt)
     ws = _workspace(nbytes, dev, workspace)
     ordc = _ORDERS[order] if isinstance(order, str) else int(order)
-    if update_mask is None:
+    if update_mask is None and eta_tok is None and loss == "mse" and not weight_norm:
         _check(lib().ttt_lact_swiglu(ctypes.byref(shape), _dt(dt), ordc, float(eta), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(W1), _ptr(W3), _ptr(W2), _ptr(O), _ptr(W1f), _ptr(W3f), _ptr(W2f),
                                      _ptr(ws), nbytes, _stream(dev)), "ttt_lact_swiglu")
         return O, W1f, W3f, W2f
-    flags = [1 if bool(x) else 0 for x in (update_mask.tolist() if hasattr(update_mask, "tolist") else update_mask)]
-    if chunk <= 0 or len(flags) != n // chunk:
-        raise ValueError(f"update_mask needs {n // chunk if chunk > 0 else 0} entries, got {len(flags)}")
-    mask = (ctypes.c_ubyte * max(1, len(flags)))(*flags)
-    _check(lib().ttt_lact_swiglu_masked(ctypes.byref(shape), _dt(dt), ordc, float(eta), _ptr(q), _ptr(k), _ptr(v),
-                                        _ptr(W1), _ptr(W3), _ptr(W2), ctypes.cast(mask, ctypes.c_void_p), _ptr(O),
-                                        _ptr(W1f), _ptr(W3f), _ptr(W2f), _ptr(ws), nbytes, _stream(dev)),
-           "ttt_lact_swiglu_masked")
+    mask = None
+    if update_mask is not None:
+        flags = [1 if bool(x) else 0 for x in
+                 (update_mask.tolist() if hasattr(update_mask, "tolist") else update_mask)]
+        if chunk <= 0 or len(flags) != n // chunk:
+            raise ValueError(f"update_mask needs {n // chunk if chunk > 0 else 0} entries, got {len(flags)}")
+        mask = (ctypes.c_ubyte * max(1, len(flags)))(*flags)
+    if eta_tok is not None:
+        _need(eta_tok, "eta_tok", (B, Hh, n), torch.float32, dev)
+    if loss not in ("mse", "dot"):
+        raise ValueError(f"loss must be 'mse' or 'dot', got {loss!r}")
+    opts = LactOptions(ordc, ctypes.cast(mask, ctypes.c_void_p) if mask is not None else None,
+                       ctypes.c_void_p(eta_tok.data_ptr()) if eta_tok is not None and eta_tok.numel() else None,
+                       1 if loss == "dot" else 0, 1 if weight_norm else 0)
+    _check(lib().ttt_lact_swiglu_ex(ctypes.byref(shape), _dt(dt), float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(W1),
+                                    _ptr(W3), _ptr(W2), ctypes.byref(opts), _ptr(O), _ptr(W1f), _ptr(W3f),
+                                    _ptr(W2f), _ptr(ws), nbytes, _stream(dev)),
+           "ttt_lact_swiglu_ex")
     return O, W1f, W3f, W2f

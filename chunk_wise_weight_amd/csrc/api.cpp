@@ -510,14 +510,21 @@ int ttt_lact_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* byt
 int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta, const void* q, const void* k,
                     const void* v, const void* W1, const void* W3, const void* W2, void* O, float* W1_f, float* W3_f,
                     float* W2_f, void* workspace, size_t workspace_bytes, void* stream) {
-  return ttt_lact_swiglu_masked(shape, dtype, order, eta, q, k, v, W1, W3, W2, nullptr, O, W1_f, W3_f, W2_f,
-                                workspace, workspace_bytes, stream);
+  ttt_lact_options opt{};
+  opt.order = order;
+  return ttt_lact_swiglu_ex(shape, dtype, eta, q, k, v, W1, W3, W2, &opt, O, W1_f, W3_f, W2_f, workspace,
+                            workspace_bytes, stream);
 }
 
-int ttt_lact_swiglu_masked(const ttt_lact_shape* shape, int dtype, int order, float eta, const void* q,
-                           const void* k, const void* v, const void* W1, const void* W3, const void* W2,
-                           const unsigned char* update_mask, void* O, float* W1_f, float* W3_f, float* W2_f,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta, const void* q, const void* k, const void* v,
+                       const void* W1, const void* W3, const void* W2, const ttt_lact_options* options, void* O,
+                       float* W1_f, float* W3_f, float* W2_f, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (options == nullptr) return TTT_ERR_ARG;
+  const int order = options->order;
+  if ((options->loss != 0 && options->loss != 1) || (options->weight_norm != 0 && options->weight_norm != 1))
+    return TTT_ERR_ARG;
+  if (options->eta_tok != nullptr && !ok_ptr(options->eta_tok)) return TTT_ERR_ARG;
   int st = check_lact(shape, dtype);
   if (st != TTT_OK) return st;
   if (order != TTT_UPDATE_THEN_APPLY && order != TTT_APPLY_THEN_UPDATE) return TTT_ERR_ARG;
@@ -532,7 +539,7 @@ int ttt_lact_swiglu_masked(const ttt_lact_shape* shape, int dtype, int order, fl
                                         : ttt::lact_workspace_bytes<float>(B, H, n, dh, m, C);
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)) return TTT_ERR_WORKSPACE;
   ttt::LactArgs a{B, H, n, dh, m, C, order, eta, q, k, v, W1, W3, W2, O, W1_f, W3_f, W2_f, (char*)workspace,
-                  update_mask};
+                  options->update_mask, options->eta_tok, options->loss, options->weight_norm};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == TTT_BF16 ? ttt::launch_lact<bf16>(a, s) : ttt::launch_lact<float>(a, s);
   if (e == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;

@@ -182,11 +182,14 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restr
 // ------------------------------------------------------------------ fwd2
 
 // Y = Hh W2^T.  P = dh rows of W2s [BH, dh, m], Q = rows of Hh (both parts).
-// Query rows: O[bh, qc C + r, :] = Y.  Key rows: R = Y - V (R [BH, C, dh]).
+// Query rows: O[bh, qc C + r, :] = Y.  Key rows: R [BH, C, dh], the gradient of
+// the chunk loss with respect to the output -- Y - V for the squared error,
+// -V for the dot-product loss (loss_dot) -- times the token's learning rate
+// eta_tok [BH, n] when given (LaCT Model Architecture §1, eq. (3)).
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __restrict__ W2s, const T* __restrict__ v,
                                        T* __restrict__ O, T* __restrict__ R, int BH, int n, int dh, int m, int C,
-                                       StepRows sr) {
+                                       StepRows sr, const float* __restrict__ eta_tok, int loss_dot) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (dh + G::BP - 1) / G::BP;
@@ -225,12 +228,16 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __rest
       if (q < 0 || q >= RPP) continue;
       // a lane outside the matrix reads the nearest valid element of V (never stored)
       const int r = min(r0 + G::acc_q(jq), nrows - 1);
+      const int64_t tok = (int64_t)bh * n + (int64_t)sr.kc * C + r;
+      const float rate = (part && eta_tok != nullptr) ? eta_tok[tok] : 1.0f;
 #pragma unroll
       for (int ib = 0; ib < G::NPB; ++ib) {
         f32x4 y = acc[ib][jq];
         if (part) {
           const int i = min(i0 + G::acc_p(ib, 0), dh - 4);
-          y -= load4(v + ((int64_t)bh * n + (int64_t)sr.kc * C + r) * dh + i);
+          const f32x4 vv = load4(v + tok * dh + i);
+          y = loss_dot ? -vv : y - vv;
+          y *= rate;
         }
         st.put4(q, G::acc_p(ib, 0), y[0], y[1], y[2], y[3]);
       }
@@ -407,6 +414,36 @@ __global__ __launch_bounds__(256) void k_lact_update(const float* __restrict__ p
   store4(Ws, x[0], x[1], x[2], x[3]);
 }
 
+// L2 weight normalisation after an update (LaCT Model Architecture §2): every
+// row of W1, W3 [m, dh] and of W2 [dh, m] -- each matrix's input dimension -- is
+// scaled to unit norm, in the fp32 state and its operand copy.  One wave per
+// row; grid.x covers 4 rows per block, grid.y = 3 BH (matrix w of row bh).
+template <typename T>
+__global__ __launch_bounds__(256) void k_lact_wnorm(float* __restrict__ W1f, float* __restrict__ W3f,
+                                                    float* __restrict__ W2f, T* __restrict__ W1s, T* __restrict__ W3s,
+                                                    T* __restrict__ W2s, int dh, int m) {
+  const int bh = blockIdx.y / 3, w = blockIdx.y % 3;
+  const int rows = w == 2 ? dh : m, len = w == 2 ? m : dh;
+  const int row = blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t o = (int64_t)bh * m * dh + (int64_t)row * len;
+  float* Wf = (w == 0 ? W1f : (w == 1 ? W3f : W2f)) + o;
+  T* Ws = (w == 0 ? W1s : (w == 1 ? W3s : W2s)) + o;
+  float ss = 0.f;
+  for (int i = lane * 4; i < len; i += 256) {
+    const f32x4 x = load4(Wf + i);
+    ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+  for (int i = lane * 4; i < len; i += 256) {
+    const f32x4 x = load4(Wf + i) * inv;
+    store4(Wf + i, x[0], x[1], x[2], x[3]);
+    store4(Ws + i, x[0], x[1], x[2], x[3]);
+  }
+}
+
 // Initial state of every (batch row, head) of a group that starts at row bh0,
 // from the heads' initial weights.
 template <typename T>
@@ -523,6 +560,7 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
   float* W1f = a.W1f + bh0 * md;
   float* W3f = a.W3f + bh0 * md;
   float* W2f = a.W2f + bh0 * md;
+  const float* eta_tok = a.eta_tok != nullptr ? a.eta_tok + (int64_t)bh0 * n : nullptr;
   const dim3 ew((unsigned)cdiv(md / 4, 256), (unsigned)(BH * 3));
   hipError_t e;
 
@@ -552,8 +590,9 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
                                                                                    dh, m, C, sr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int tq2 = (int)(cdiv(sr.nq, Wide::BQ) + cdiv(sr.nk, Wide::BQ));
-    if (want()) k_lact_fwd2<T><<<(unsigned)(cdiv(dh, Wide::BP) * tq2 * BH), Wide::NT, 0, s>>>(Hh, W2s, v, O, R, BH, n, dh, m, C,
-                                                                                sr);
+    if (want())
+      k_lact_fwd2<T><<<(unsigned)(cdiv(dh, Wide::BP) * tq2 * BH), Wide::NT, 0, s>>>(Hh, W2s, v, O, R, BH, n, dh, m, C,
+                                                                                 sr, eta_tok, a.loss_dot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (sr.nk == 0) continue;
     if (want()) k_lact_dh<T><<<(unsigned)(cdiv(m, Wide::BP) * cdiv(sr.nk, Wide::BQ) * BH), Wide::NT, 0, s>>>(
@@ -564,6 +603,10 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
     if (want()) k_lact_grad<T><<<(unsigned)tg, Wide::NT, 0, s>>>(kk, dA, dU, Hh, R, part, BH, n, dh, m, C, sr.kc, sr.nk, kslice);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (want()) k_lact_update<T><<<ew, 256, 0, s>>>(part, W1f, W3f, W2f, W1s, W3s, W2s, BH, dh, m, a.eta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (a.weight_norm && want())
+      k_lact_wnorm<T><<<dim3((unsigned)cdiv(dh > m ? dh : m, 4), (unsigned)(BH * 3)), 256, 0, s>>>(
+          W1f, W3f, W2f, W1s, W3s, W2s, dh, m);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

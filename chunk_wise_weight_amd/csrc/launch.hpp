@@ -71,6 +71,9 @@ struct LactArgs {
   float *W1f, *W3f, *W2f;
   char* ws;
   const unsigned char* update_mask;   // HOST [n / C]: chunks whose keys update the weights; null = every chunk
+  const float* eta_tok;               // DEVICE [B, H, n] per-token learning rates, or null
+  int loss_dot;                       // 1: dot-product loss -f(k)^T v; 0: squared error
+  int weight_norm;                    // 1: L2-normalise the rows of W1, W3, W2 after every update
 };
 template <typename T>
 size_t lact_workspace_bytes(int B, int H, int n, int dh, int m, int C);

@@ -275,24 +275,42 @@ int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta
                     void* O, float* W1_f, float* W3_f, float* W2_f,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* The same layer with a strided update (review of "Test-Time Training Done
- * Right", LaCT Model Architecture §1 on the order of the apply and update
- * operations: updating on some chunks only while applying all of them gives a
- * strided block-wise causal mask; its video use updates on clean chunks).
- *   update_mask  [n / chunk] uint8, HOST memory read during the call, shared
- *                by every (batch, head) row: chunk c's keys and values take
- *                the gradient step only where update_mask[c] != 0; every
- *                chunk's queries are applied.  NULL: every chunk updates
- *                (ttt_lact_swiglu).  The mask decides which launches are
- *                enqueued, so a captured graph keeps the mask it was
- *                captured with.
- * Same arguments, workspace and errors as ttt_lact_swiglu otherwise. */
-int ttt_lact_swiglu_masked(const ttt_lact_shape* shape, int dtype, int order, float eta,
-                           const void* q, const void* k, const void* v,
-                           const void* W1, const void* W3, const void* W2,
-                           const unsigned char* update_mask,
-                           void* O, float* W1_f, float* W3_f, float* W2_f,
-                           void* workspace, size_t workspace_bytes, void* stream);
+/* Options of ttt_lact_swiglu_ex (zero-initialise, then set what is needed). */
+typedef struct {
+  /* TTT_UPDATE_THEN_APPLY (0) or TTT_APPLY_THEN_UPDATE (1), as in ttt_lact_swiglu. */
+  int order;
+  /* Strided update (review of "Test-Time Training Done Right", LaCT Model
+   * Architecture §1 on the order of the apply and update operations: updating
+   * on some chunks only while applying all of them gives a strided
+   * block-wise causal mask; its video use updates on clean chunks).
+   * [n / chunk] uint8, HOST memory read during the call, shared by every
+   * (batch, head) row: chunk c's keys and values take the gradient step only
+   * where update_mask[c] != 0; every chunk's queries are applied.  NULL:
+   * every chunk updates.  The mask decides which launches are enqueued, so a
+   * captured graph keeps the mask it was captured with. */
+  const unsigned char* update_mask;
+  /* Per-token learning rates eta_i weighting each token's loss in the
+   * gradient (§1, eq. (3)), on top of the scalar eta: [B, H, n] fp32, DEVICE,
+   * 16-byte aligned.  NULL: all 1. */
+  const float* eta_tok;
+  /* 0: the squared error (1/2)||f_W(k) - v||^2 of ttt_lact_swiglu; 1: the
+   * dot-product loss -f_W(k)^T v (§1).  Other values: TTT_ERR_ARG. */
+  int loss;
+  /* 1: after every update, L2-normalise each row of W1, W3 (over head_dim)
+   * and of W2 (over hidden) -- the input dimension of each matrix (§2,
+   * fast-weight normalisation); the final states are normalised too.  0: no
+   * normalisation.  Other values: TTT_ERR_ARG.  (Muon is not provided.) */
+  int weight_norm;
+} ttt_lact_options;
+
+/* The LaCT layer of ttt_lact_swiglu with options (above; NULL options:
+ * TTT_ERR_ARG); same arguments, workspace and errors otherwise. */
+int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta,
+                       const void* q, const void* k, const void* v,
+                       const void* W1, const void* W3, const void* W2,
+                       const ttt_lact_options* options,
+                       void* O, float* W1_f, float* W3_f, float* W2_f,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -106,7 +106,7 @@ def test_lact_rows_equal_single_row_calls(B, H):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
 def test_lact_update_mask(dtype, order):
-    """Strided update (ttt_lact_swiglu_masked): only the flagged chunks take the gradient step, every chunk is
+    """Strided update (ttt_lact_swiglu_ex, option update_mask): only the flagged chunks take the gradient step, every chunk is
     applied, against the oracle with the same mask on 2 x 2 rows (both stream groups); the first chunk is masked,
     which leaves the first update-then-apply step with nothing to do.  An all-on mask gives the unmasked call's
     bits."""
@@ -129,6 +129,44 @@ def test_lact_update_mask(dtype, order):
         errs[name] = rel(f64(t), want)
         errs[name + "_delta"] = rel(f64(t) - w0, want - w0)
     assert all(e < tol for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
+@pytest.mark.parametrize("variant", ["eta_tok", "dot", "weight_norm", "all"])
+def test_lact_update_variants(dtype, order, variant):
+    """LaCT's update variants (ttt_lact_swiglu_ex): per-token learning rates, the dot-product loss, L2 weight
+    normalisation after each update, and all three with an update mask, against the oracle on 2 heads."""
+    cfg = cfg_small(dtype, order, B=1, H=2, n=512, dh=64, m=128, C=128, seed=23,
+                    eta=0.1 if variant in ("dot", "all") else 0.6)
+    x = ti.lact_inputs(cfg)
+    g = {k: v.cuda() for k, v in x.items()}
+    rates = np.random.default_rng(24).uniform(0.2, 1.2, size=(cfg.batch, cfg.heads, cfg.seq_len))
+    kw, okw = {}, {}
+    if variant in ("eta_tok", "all"):
+        kw["eta_tok"] = torch.from_numpy(rates).float().cuda()
+        okw["eta_tok"] = kw["eta_tok"].double().cpu().numpy()      # the rates the kernel sees (fp32)
+    if variant in ("dot", "all"):
+        kw["loss"] = okw["loss"] = "dot"
+    if variant in ("weight_norm", "all"):
+        kw["weight_norm"] = okw["weight_norm"] = True
+    if variant == "all":
+        kw["update_mask"] = okw["update_mask"] = [1, 0, 1, 1]
+    got = cw.ttt_lact_swiglu(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta, cfg.order, **kw)
+    torch.cuda.synchronize()
+    Oref, W1r, W3r, W2r = olact.lact_layer(*(ti.to_f64(x[k]) for k in ("q", "k", "v", "W1", "W3", "W2")), cfg.chunk,
+                                           cfg.eta, cfg.order, **okw)
+    tol = TOL[dtype]
+    errs = {"O": rel(f64(got[0]), Oref)}
+    for name, t, want, init in (("W1", got[1], W1r, x["W1"]), ("W3", got[2], W3r, x["W3"]),
+                                ("W2", got[3], W2r, x["W2"])):
+        w0 = ti.to_f64(init)[None]
+        errs[name] = rel(f64(t), want)
+        errs[name + "_delta"] = rel(f64(t) - w0, want - w0)
+    assert all(e < tol for e in errs.values()), errs
+    if variant in ("weight_norm", "all"):
+        for t in got[1:]:
+            assert torch.allclose(t.norm(dim=-1), torch.ones((), device=t.device), atol=1e-5)
 
 
 def test_lact_single_chunk_full_batch_step():

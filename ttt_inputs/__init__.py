@@ -105,6 +105,9 @@ class LactConfig:
     var_w3: float | None = None   # default 1/head_dim
     var_w2: float | None = None   # default 1/hidden
     update_every: int = 1         # only every update_every-th chunk takes the update step (1: all)
+    loss: str = "mse"             # "mse" or "dot" (the dot-product loss -f(k)^T v)
+    weight_norm: bool = False     # L2-normalise the weight rows after every update
+    token_rates: bool = False     # draw per-token learning rates eta_tok ~ U(0, 1) (fp32)
 
     @property
     def tokens(self) -> int:
@@ -126,7 +129,8 @@ class LactConfig:
         6*dh*m on every chunk."""
         mask = self.update_mask()
         upd = 1.0 if mask is None else sum(mask) / len(mask)
-        return float(self.tokens) * self.heads * (6.0 + 14.0 * upd) * self.head_dim * self.hidden
+        key = 14.0 - (2.0 if self.loss == "dot" else 0.0)     # the dot loss needs no key output f(k)
+        return float(self.tokens) * self.heads * (6.0 + key * upd) * self.head_dim * self.hidden
 
     def with_(self, **kw) -> "LactConfig":
         return replace(self, **kw)
@@ -149,6 +153,9 @@ WORKLOADS = {
                                              seed=1002, docs=8),
     "mse_bf16_4x64k": InplaceConfig("mse_bf16_4x64k", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16", seed=1003),
     "lact_bf16_256k": LactConfig("lact_bf16_256k", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004),
+    # the LaCT review's own update: dot-product loss, per-token learning rates, L2 weight normalisation
+    "lact_bf16_256k_paper": LactConfig("lact_bf16_256k_paper", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
+                                       loss="dot", weight_norm=True, token_rates=True),
     # the same with the update on every other chunk only (a strided block-wise mask)
     "lact_bf16_256k_strided": LactConfig("lact_bf16_256k_strided", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
                                          update_every=2),
@@ -199,7 +206,8 @@ def lact_inputs(cfg: LactConfig, seed: int | None = None) -> dict:
     """Draw the LaCT layer inputs on the CPU.
 
     Returns q, k, v [B, H, n, dh] (L2-normalised over dh per token, then
-    rounded), W1, W3 [H, m, dh], W2 [H, dh, m].
+    rounded), W1, W3 [H, m, dh], W2 [H, dh, m], and with token_rates the
+    per-token learning rates eta_tok [B, H, n] (fp32, U(0, 1)), drawn last.
     """
     gen = torch.Generator(device="cpu")
     gen.manual_seed(cfg.seed if seed is None else seed)
@@ -213,6 +221,8 @@ def lact_inputs(cfg: LactConfig, seed: int | None = None) -> dict:
     out["W1"] = _draw(gen, (Hh, m, dh), cfg.var_w1 if cfg.var_w1 is not None else 1.0 / dh, dt)
     out["W3"] = _draw(gen, (Hh, m, dh), cfg.var_w3 if cfg.var_w3 is not None else 1.0 / dh, dt)
     out["W2"] = _draw(gen, (Hh, dh, m), cfg.var_w2 if cfg.var_w2 is not None else 1.0 / m, dt)
+    if cfg.token_rates:
+        out["eta_tok"] = torch.rand(B, Hh, n, generator=gen, dtype=torch.float32)
     return out
 
 
