@@ -23,7 +23,13 @@ fast-weight normalisation), each off by default:
     output is -v in place of the residual f_W(k) - v;
   * L2 weight normalisation after each update, along each matrix's input
     dimension: every row of W1, W3 (over d_h) and of W2 (over the hidden
-    width) is scaled to unit norm.  Muon is not provided.
+    width) is scaled to unit norm;
+  * the Muon update rule (§2): each gradient replaced by Muon(g) ~ U V^T
+    before the step.  The page names the Newton-Schulz iteration without its
+    polynomial; the quintic iteration and its coefficients are those
+    published with the Muon optimizer (K. Jordan et al., "Muon: An optimizer
+    for hidden layers in neural networks", 2024): X = g / ||g||_F on the wide
+    orientation, five times X <- a X + (b A + c A^2) X with A = X X^T.
 """
 from __future__ import annotations
 
@@ -31,7 +37,7 @@ import numpy as np
 
 from .inplace import silu
 
-__all__ = ["swiglu_apply", "swiglu_loss", "swiglu_grads", "l2_normalize_rows", "lact_layer"]
+__all__ = ["swiglu_apply", "swiglu_loss", "swiglu_grads", "muon", "l2_normalize_rows", "lact_layer"]
 
 
 def _f64(a):
@@ -79,6 +85,28 @@ def swiglu_grads(kc, vc, W1, W3, W2, eta_tok=None, loss="mse"):
     return G1, G3, G2
 
 
+MUON_COEFFS = (3.4445, -4.7750, 2.0315)
+MUON_STEPS = 5
+
+
+def muon(g):
+    """Newton-Schulz orthogonalisation of a gradient (see the module notes):
+    g [r, c] is scaled to unit Frobenius norm, taken as [min, max] (transposed
+    when r > c), iterated MUON_STEPS times X <- a X + (b A + c A^2) X with
+    A = X X^T, and returned in g's orientation.  It approximates the polar
+    factor U V^T of g = U S V^T."""
+    g = _f64(g)
+    a, b, c = MUON_COEFFS
+    X = g / (np.linalg.norm(g) + 1e-7)
+    tall = X.shape[0] > X.shape[1]
+    if tall:
+        X = X.T
+    for _ in range(MUON_STEPS):
+        A = X @ X.T
+        X = a * X + (b * A + c * (A @ A)) @ X
+    return X.T if tall else X
+
+
 def l2_normalize_rows(W):
     """Each row of W scaled to unit L2 norm (the fast-weight normalisation of
     LaCT Model Architecture §2, along the input dimension of W [out, in])."""
@@ -87,7 +115,7 @@ def l2_normalize_rows(W):
 
 
 def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply", update_mask=None, eta_tok=None,
-               loss="mse", weight_norm=False):
+               loss="mse", weight_norm=False, use_muon=False):
     """LaCT layer over chunks.  q, k, v [B, H, n, dh]; W1, W3 [H, m, dh];
     W2 [H, dh, m].  Returns (O [B, H, n, dh], W1_f, W3_f [B, H, m, dh],
     W2_f [B, H, dh, m]).
@@ -99,8 +127,9 @@ def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply", updat
     clean chunks only).
 
     `eta_tok` [B, H, n] gives per-token learning rates, `loss` is "mse" or
-    "dot", and `weight_norm` L2-normalises the rows of each matrix after every
-    update (see the module notes)."""
+    "dot", `weight_norm` L2-normalises the rows of each matrix after every
+    update, and `use_muon` steps along Muon(g) instead of g (see the module
+    notes)."""
     q, k, v = _f64(q), _f64(k), _f64(v)
     W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
     B, Hn, n, dh = q.shape
@@ -118,6 +147,8 @@ def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply", updat
                 if update_mask is None or update_mask[c]:
                     et = None if eta_tok is None else _f64(eta_tok)[b, h, r]
                     g1, g3, g2 = swiglu_grads(k[b, h, r], v[b, h, r], w1, w3, w2, et, loss)
+                    if use_muon:
+                        g1, g3, g2 = muon(g1), muon(g3), muon(g2)
                     w1, w3, w2 = w1 - eta * g1, w3 - eta * g3, w2 - eta * g2
                     if weight_norm:
                         w1, w3, w2 = l2_normalize_rows(w1), l2_normalize_rows(w3), l2_normalize_rows(w2)

@@ -217,3 +217,35 @@ def test_weight_norm_matches_torch_normalize():
     _, W1f, W3f, W2f = orc.lact_layer(q, k, v, W1, W3, W2, 3, eta, weight_norm=True)
     for W in (W1f, W3f, W2f):
         np.testing.assert_allclose(np.linalg.norm(W, axis=-1), 1.0, rtol=1e-12)
+
+
+@pytest.mark.parametrize("shape", [(6, 4), (4, 6), (5, 5)])
+def test_muon_acts_on_singular_values(shape):
+    """An odd matrix polynomial acts on each singular value alone, so the Newton-Schulz iteration equals
+    U p(...p(s / ||g||_F)) V^T from numpy's SVD of g, with p the quintic a x + b x^3 + c x^5; and it lands near
+    the polar factor U V^T (every singular value of the result within [0.6, 1.25])."""
+    g = np.random.default_rng(40).standard_normal(shape)
+    U, S, Vt = np.linalg.svd(g, full_matrices=False)
+    a, b, c = orc.MUON_COEFFS
+    x = S / (np.linalg.norm(g) + 1e-7)
+    for _ in range(orc.MUON_STEPS):
+        x = a * x + b * x ** 3 + c * x ** 5
+    want = (U * x) @ Vt
+    got = orc.muon(g)
+    np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+    sv = np.linalg.svd(got, compute_uv=False)
+    assert sv.min() > 0.6 and sv.max() < 1.25, sv
+
+
+def test_muon_update_in_the_layer():
+    """One chunk: W_final = W - eta Muon(g) with g from torch autograd; the queries see it."""
+    q, k, v, W1, W3, W2 = _problem(41, H=1, n=10)
+    eta = 0.05
+    O, W1f, W3f, W2f = orc.lact_layer(q, k, v, W1, W3, W2, 10, eta, use_muon=True)
+    w1, w3, w2 = (torch.from_numpy(a[0].copy()).requires_grad_(True) for a in (W1, W3, W2))
+    (0.5 * ((_torch_swiglu(torch.from_numpy(k[0, 0]), w1, w3, w2) - torch.from_numpy(v[0, 0])) ** 2).sum()).backward()
+    n1, n3, n2 = (w.detach().numpy() - eta * orc.muon(w.grad.numpy()) for w in (w1, w3, w2))
+    for got, want in ((W1f[0, 0], n1), (W3f[0, 0], n3), (W2f[0, 0], n2)):
+        np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-13)
+    ref = _torch_swiglu(*(torch.from_numpy(a) for a in (q[0, 0], n1, n3, n2))).numpy()
+    np.testing.assert_allclose(O[0, 0], ref, rtol=1e-11, atol=1e-13)
