@@ -148,7 +148,7 @@ def bench_generic(cfg, steps, warmup):
         g = {k: v.cuda() for k, v in x.items()}
         call = lambda: cw.ttt_lact_swiglu(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta,
                                           cfg.order, update_mask=cfg.update_mask(), eta_tok=g.get("eta_tok"),
-                                          loss=cfg.loss, weight_norm=cfg.weight_norm)
+                                          loss=cfg.loss, weight_norm=cfg.weight_norm, muon=cfg.muon)
     else:
         x = ti.inplace_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
@@ -204,7 +204,7 @@ def cpu_baseline(cfg, target_s):
                                           update_mask=None if umask is None else umask[:kc],
                                           eta_tok=(ti.to_f64(x["eta_tok"][:, :1, : kc * cfg.chunk])
                                                    if cfg.token_rates else None),
-                                          loss=cfg.loss, weight_norm=cfg.weight_norm)
+                                          loss=cfg.loss, weight_norm=cfg.weight_norm, use_muon=cfg.muon)
         per_tok_heads = 1
     else:
         x = ti.inplace_inputs(cfg)
@@ -273,8 +273,9 @@ def main():
                          "order": cfg.order}
         if cfg.update_every > 1:
             out["config"]["update_every"] = cfg.update_every
-        if cfg.loss != "mse" or cfg.weight_norm or cfg.token_rates:
-            out["config"].update({"loss": cfg.loss, "weight_norm": cfg.weight_norm, "token_rates": cfg.token_rates})
+        if cfg.loss != "mse" or cfg.weight_norm or cfg.token_rates or cfg.muon:
+            out["config"].update({"loss": cfg.loss, "weight_norm": cfg.weight_norm, "token_rates": cfg.token_rates,
+                                  "muon": cfg.muon})
     else:
         out["config"] = {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_len, "d_model": cfg.d_model,
                          "d_ff": cfg.d_ff, "chunk": cfg.chunk, "conv_k": cfg.conv_k, "eta": cfg.eta,

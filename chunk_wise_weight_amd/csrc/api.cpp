@@ -522,7 +522,8 @@ int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta, const 
                        void* stream) {
   if (options == nullptr) return TTT_ERR_ARG;
   const int order = options->order;
-  if ((options->loss != 0 && options->loss != 1) || (options->weight_norm != 0 && options->weight_norm != 1))
+  if ((options->loss != 0 && options->loss != 1) || (options->weight_norm != 0 && options->weight_norm != 1) ||
+      (options->muon != 0 && options->muon != 1))
     return TTT_ERR_ARG;
   if (options->eta_tok != nullptr && !ok_ptr(options->eta_tok)) return TTT_ERR_ARG;
   int st = check_lact(shape, dtype);
@@ -539,7 +540,7 @@ int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta, const 
                                         : ttt::lact_workspace_bytes<float>(B, H, n, dh, m, C);
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)) return TTT_ERR_WORKSPACE;
   ttt::LactArgs a{B, H, n, dh, m, C, order, eta, q, k, v, W1, W3, W2, O, W1_f, W3_f, W2_f, (char*)workspace,
-                  options->update_mask, options->eta_tok, options->loss, options->weight_norm};
+                  options->update_mask, options->eta_tok, options->loss, options->weight_norm, options->muon};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == TTT_BF16 ? ttt::launch_lact<bf16>(a, s) : ttt::launch_lact<float>(a, s);
   if (e == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;

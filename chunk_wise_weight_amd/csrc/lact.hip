@@ -37,8 +37,10 @@ constexpr int kSplit = 2;              // token splits of the weight-gradient GE
 
 // Workspace layout (byte offsets), one region per buffer.
 struct LactWs {
-  size_t Hh, A, U, R, dA, dU, W1s, W3s, W2s, part, total;
+  size_t Hh, A, U, R, dA, dU, W1s, W3s, W2s, part, mX0, mX1, mA, mB, mnorm, total;
 };
+
+constexpr int kMuonNormBlocks = 64;     // partial sums of squares per gradient
 
 inline size_t al(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -57,6 +59,13 @@ LactWs lact_layout(int bh_rows, int dh, int m, int C) {
   w.W3s = o;  o += al(BH * md * e);
   w.W2s = o;  o += al(BH * md * e);
   w.part = o; o += al((size_t)kSplit * BH * 3 * md * 4);   // split-token gradient partials
+  // Muon: iterates X (two, ping-pong) [3 BH, r, c], A and B [3 BH, r, r], norm partials
+  const size_t r = (size_t)(m < dh ? m : dh);
+  w.mX0 = o;  o += al(3 * BH * md * e);
+  w.mX1 = o;  o += al(3 * BH * md * e);
+  w.mA = o;   o += al(3 * BH * r * r * e);
+  w.mB = o;   o += al(3 * BH * r * r * e);
+  w.mnorm = o; o += al(3 * BH * kMuonNormBlocks * 4);
   w.total = o;
   return w;
 }
@@ -444,6 +453,154 @@ __global__ __launch_bounds__(256) void k_lact_wnorm(float* __restrict__ W1f, flo
   }
 }
 
+// ------------------------------------------------------------------ Muon
+
+// The Muon update rule (LaCT Model Architecture §2): each gradient g is replaced
+// by Muon(g) ~ U V^T before the step.  The page names Newton-Schulz without its
+// polynomial; this is the quintic iteration with the coefficients published
+// with the Muon optimizer: X = g / ||g||_F in the wide orientation [r, c]
+// (r = min(m, dh), c = max(m, dh)), then five times A = X X^T,
+// B = b A + c A^2, X <- a X + B X, stored in the operand dtype with fp32
+// accumulation.  The 3 BH gradients of a step (matrix mat = 3 bh + w) form one
+// batch.
+constexpr float kMuonA = 3.4445f, kMuonB = -4.7750f, kMuonC = 2.0315f;
+constexpr int kMuonSteps = 5;
+
+// Gradient w is [m, dh] for W1, W3 and [dh, m] for W2; tall ones are iterated
+// transposed.
+__host__ __device__ inline bool muon_tall(int w, int dh, int m) { return w < 2 ? m > dh : dh > m; }
+
+// Partial sums of squares of g (the sum of the split partials), kMuonNormBlocks
+// per gradient.
+__global__ __launch_bounds__(256) void k_muon_norm(const float* __restrict__ part, float* __restrict__ normp, int BH,
+                                                   int64_t md) {
+  const int mat = blockIdx.y, bh = mat / 3, w = mat % 3;
+  float ss = 0.f;
+  for (int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; e < md; e += (int64_t)kMuonNormBlocks * 1024) {
+    f32x4 g = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSplit; ++s) g += load4(part + (((int64_t)s * BH + bh) * 3 + w) * md + e);
+    ss += g[0] * g[0] + g[1] * g[1] + g[2] * g[2] + g[3] * g[3];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  __shared__ float wsum[4];
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) normp[mat * kMuonNormBlocks + blockIdx.x] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+}
+
+// X0 = g / (||g||_F + 1e-7) in the wide orientation [r, c], one element per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void k_muon_prep(const float* __restrict__ part, const float* __restrict__ normp,
+                                                   T* __restrict__ X, int BH, int dh, int m) {
+  const int mat = blockIdx.y, bh = mat / 3, w = mat % 3;
+  const int r = m < dh ? m : dh, c = m < dh ? dh : m;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x, md = (int64_t)m * dh;
+  if (idx >= md) return;
+  const int i = (int)(idx / c), j = (int)(idx % c);
+  float ss = 0.f;
+  for (int t = 0; t < kMuonNormBlocks; ++t) ss += normp[mat * kMuonNormBlocks + t];
+  const float inv = 1.0f / (sqrtf(ss) + 1e-7f);
+  // g is [c, r] when tall (X = g^T), else [r, c]
+  const int64_t ge = muon_tall(w, dh, m) ? (int64_t)j * r + i : (int64_t)i * c + j;
+  float g = 0.f;
+#pragma unroll
+  for (int s = 0; s < kSplit; ++s) g += part[(((int64_t)s * BH + bh) * 3 + w) * md + ge];
+  X[(int64_t)mat * md + idx] = from_f32<T>(g * inv);
+}
+
+// One GEMM of a Newton-Schulz step for every gradient of the batch (grid.y):
+//   STEP 0: A = X X^T                  P = X rows,            Q = X rows,  K = c
+//   STEP 1: B = b A + c A A^T (= A^2)  P = A rows,            Q = A rows,  K = r
+//   STEP 2: Xn = a X + B X             P = X columns (MN),    Q = B rows,  K = r
+// Output row-major, rows indexed by Q and columns by P, so that a lane's four
+// accumulators are four consecutive elements of one row.
+template <typename T, int STEP>
+TTT_GEMM_KERNEL(Wide) void k_ns_gemm(const T* __restrict__ X, const T* __restrict__ A, const T* __restrict__ Bm,
+                                     T* __restrict__ out, int r, int c) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int mat = blockIdx.y;
+  const int cols = STEP == 2 ? c : r, rows = r;
+  const int TP = (cols + G::BP - 1) / G::BP, TQ = (rows + G::BQ - 1) / G::BQ;
+  int tp, tq;
+  grouped_tile((int)blockIdx.x, TP, TQ, 4, tp, tq);
+  const int p0 = tp * G::BP, q0 = tq * G::BQ;
+  const T* x = X + (int64_t)mat * r * c;
+  const T* a = A + (int64_t)mat * r * r;
+  typename G::Frag acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  if constexpr (STEP == 0) {
+    const uint64_t ld = (uint64_t)c * esz<T>();
+    DmaOp<G::NW, G::BP> op;
+    DmaOp<G::NW, G::BQ> oq;
+    op.init(x + (int64_t)p0 * c, nullptr, min(G::BP, cols - p0), ld, (unsigned)ld);
+    oq.init(x + (int64_t)q0 * c, nullptr, min(G::BQ, rows - q0), ld, (unsigned)ld);
+    mainloop<T, G>(op, oq, (int)((ld + 127) / 128), acc, smem, NoHook{});
+  } else if constexpr (STEP == 1) {
+    const uint64_t ld = (uint64_t)r * esz<T>();
+    DmaOp<G::NW, G::BP> op;
+    DmaOp<G::NW, G::BQ> oq;
+    op.init(a + (int64_t)p0 * r, nullptr, min(G::BP, cols - p0), ld, (unsigned)ld);
+    oq.init(a + (int64_t)q0 * r, nullptr, min(G::BQ, rows - q0), ld, (unsigned)ld);
+    mainloop<T, G>(op, oq, (int)((ld + 127) / 128), acc, smem, NoHook{});
+  } else {
+    const uint64_t ld = (uint64_t)r * esz<T>();
+    DmaOpMN<T, G::NW, G::BP> op;
+    DmaOp<G::NW, G::BQ> oq;
+    op.init(x + p0, min(G::BP, cols - p0), (uint64_t)c * esz<T>(), r);
+    oq.init(Bm + (int64_t)mat * r * r + (int64_t)q0 * r, nullptr, min(G::BQ, rows - q0), ld, (unsigned)ld);
+    mainloop<T, G>(op, oq, (r + DmaOpMN<T, G::NW, G::BP>::KR - 1) / DmaOpMN<T, G::NW, G::BP>::KR, acc, smem,
+                   NoHook{});
+  }
+  T* o = out + (int64_t)mat * rows * cols;
+#pragma unroll
+  for (int jq = 0; jq < G::NQB; ++jq) {
+    const int q = q0 + G::acc_q(jq);
+    if (q >= rows) continue;
+#pragma unroll
+    for (int ib = 0; ib < G::NPB; ++ib) {
+      const int p = p0 + G::acc_p(ib, 0);
+      if (p >= cols) continue;                          // cols % 8 == 0: p .. p + 3 inside
+      f32x4 v = acc[ib][jq];
+      if constexpr (STEP == 1) v = kMuonC * v + kMuonB * load4(a + (int64_t)q * r + p);
+      if constexpr (STEP == 2) v = v + kMuonA * load4(x + (int64_t)q * c + p);
+      store4(o + (int64_t)q * cols + p, v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// W -= eta Muon(g): the final iterate X, transposed back for tall gradients;
+// fp32 state and its operand copy, four elements per thread, grid.y = 3 BH.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lact_update_muon(const T* __restrict__ X, float* __restrict__ W1f,
+                                                          float* __restrict__ W3f, float* __restrict__ W2f,
+                                                          T* __restrict__ W1s, T* __restrict__ W3s,
+                                                          T* __restrict__ W2s, int dh, int m, float eta) {
+  const int64_t md = (int64_t)m * dh;
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= md) return;
+  const int mat = blockIdx.y, bh = mat / 3, w = mat % 3;
+  const int cw_ = w == 2 ? m : dh;                     // columns of W (and of g)
+  const int c = m < dh ? dh : m;
+  const T* x = X + (int64_t)mat * md;
+  f32x4 u;
+  if (muon_tall(w, dh, m)) {                          // W[i][j] -= eta X[j][i]
+    const int i = (int)(e / cw_), j = (int)(e % cw_);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) u[t] = to_f32(x[(int64_t)(j + t) * c + i]);
+  } else {
+    u = load4(x + e);
+  }
+  float* Wf = (w == 0 ? W1f : (w == 1 ? W3f : W2f)) + (int64_t)bh * md + e;
+  T* Ws = (w == 0 ? W1s : (w == 1 ? W3s : W2s)) + (int64_t)bh * md + e;
+  f32x4 v = load4(Wf);
+  v -= eta * u;
+  store4(Wf, v[0], v[1], v[2], v[3]);
+  store4(Ws, v[0], v[1], v[2], v[3]);
+}
+
 // Initial state of every (batch row, head) of a group that starts at row bh0,
 // from the heads' initial weights.
 template <typename T>
@@ -553,6 +710,12 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
   T* W3s = (T*)(wsg + L.W3s);
   T* W2s = (T*)(wsg + L.W2s);
   float* part = (float*)(wsg + L.part);
+  T* mX0 = (T*)(wsg + L.mX0);
+  T* mX1 = (T*)(wsg + L.mX1);
+  T* mA = (T*)(wsg + L.mA);
+  T* mB = (T*)(wsg + L.mB);
+  float* mnorm = (float*)(wsg + L.mnorm);
+  const int mr = m < dh ? m : dh, mc = m < dh ? dh : m;     // Muon's wide orientation [mr, mc]
   const T* q = (const T*)a.q + io;
   const T* kk = (const T*)a.k + io;
   const T* v = (const T*)a.v + io;
@@ -602,7 +765,31 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
                        (int64_t)kSplit * BH;
     if (want()) k_lact_grad<T><<<(unsigned)tg, Wide::NT, 0, s>>>(kk, dA, dU, Hh, R, part, BH, n, dh, m, C, sr.kc, sr.nk, kslice);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (want()) k_lact_update<T><<<ew, 256, 0, s>>>(part, W1f, W3f, W2f, W1s, W3s, W2s, BH, dh, m, a.eta);
+    if (a.muon) {
+      const dim3 nsr((unsigned)(cdiv(mr, Wide::BP) * cdiv(mr, Wide::BQ)), (unsigned)(3 * BH));
+      const dim3 nsx((unsigned)(cdiv(mc, Wide::BP) * cdiv(mr, Wide::BQ)), (unsigned)(3 * BH));
+      if (want()) k_muon_norm<<<dim3(kMuonNormBlocks, (unsigned)(3 * BH)), 256, 0, s>>>(part, mnorm, BH, md);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if (want())
+        k_muon_prep<T><<<dim3((unsigned)cdiv(md, 256), (unsigned)(3 * BH)), 256, 0, s>>>(part, mnorm, mX0, BH, dh, m);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      T* xs = mX0;
+      T* xn = mX1;
+      for (int it = 0; it < kMuonSteps; ++it) {
+        if (want()) k_ns_gemm<T, 0><<<nsr, Wide::NT, 0, s>>>(xs, nullptr, nullptr, mA, mr, mc);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (want()) k_ns_gemm<T, 1><<<nsr, Wide::NT, 0, s>>>(nullptr, mA, nullptr, mB, mr, mc);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (want()) k_ns_gemm<T, 2><<<nsx, Wide::NT, 0, s>>>(xs, nullptr, mB, xn, mr, mc);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        T* t = xs;
+        xs = xn;
+        xn = t;
+      }
+      if (want()) k_lact_update_muon<T><<<ew, 256, 0, s>>>(xs, W1f, W3f, W2f, W1s, W3s, W2s, dh, m, a.eta);
+    } else if (want()) {
+      k_lact_update<T><<<ew, 256, 0, s>>>(part, W1f, W3f, W2f, W1s, W3s, W2s, BH, dh, m, a.eta);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.weight_norm && want())
       k_lact_wnorm<T><<<dim3((unsigned)cdiv(dh > m ? dh : m, 4), (unsigned)(BH * 3)), 256, 0, s>>>(

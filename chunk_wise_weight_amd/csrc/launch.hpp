@@ -74,6 +74,7 @@ struct LactArgs {
   const float* eta_tok;               // DEVICE [B, H, n] per-token learning rates, or null
   int loss_dot;                       // 1: dot-product loss -f(k)^T v; 0: squared error
   int weight_norm;                    // 1: L2-normalise the rows of W1, W3, W2 after every update
+  int muon;                           // 1: step along Muon(g) (Newton-Schulz) instead of g
 };
 template <typename T>
 size_t lact_workspace_bytes(int B, int H, int n, int dh, int m, int C);

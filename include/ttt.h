@@ -299,8 +299,16 @@ typedef struct {
   /* 1: after every update, L2-normalise each row of W1, W3 (over head_dim)
    * and of W2 (over hidden) -- the input dimension of each matrix (§2,
    * fast-weight normalisation); the final states are normalised too.  0: no
-   * normalisation.  Other values: TTT_ERR_ARG.  (Muon is not provided.) */
+   * normalisation.  Other values: TTT_ERR_ARG. */
   int weight_norm;
+  /* 1: the Muon update rule (§2): each gradient g is replaced by Muon(g) ~
+   * U V^T before the step (and before weight_norm).  The page names the
+   * Newton-Schulz iteration without its polynomial; this is the quintic one
+   * published with the Muon optimizer (coefficients 3.4445, -4.7750, 2.0315,
+   * five steps on g / ||g||_F taken as [min(m, dh), max(m, dh)]), run in the
+   * layer's dtype with fp32 accumulation.  0: plain gradient.  Other values:
+   * TTT_ERR_ARG. */
+  int muon;
 } ttt_lact_options;
 
 /* The LaCT layer of ttt_lact_swiglu with options (above; NULL options:

@@ -133,12 +133,14 @@ def test_lact_update_mask(dtype, order):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
-@pytest.mark.parametrize("variant", ["eta_tok", "dot", "weight_norm", "all"])
+@pytest.mark.parametrize("variant", ["eta_tok", "dot", "weight_norm", "all", "muon", "muon_weight_norm"])
 def test_lact_update_variants(dtype, order, variant):
     """LaCT's update variants (ttt_lact_swiglu_ex): per-token learning rates, the dot-product loss, L2 weight
-    normalisation after each update, and all three with an update mask, against the oracle on 2 heads."""
+    normalisation after each update, all three with an update mask, and the Muon rule (Newton-Schulz on the
+    gradients, dh 64 < m 128 so W1 and W3's gradients are iterated transposed) with and without normalisation,
+    against the oracle on 2 heads."""
     cfg = cfg_small(dtype, order, B=1, H=2, n=512, dh=64, m=128, C=128, seed=23,
-                    eta=0.1 if variant in ("dot", "all") else 0.6)
+                    eta={"dot": 0.1, "all": 0.1, "muon": 0.05, "muon_weight_norm": 0.05}.get(variant, 0.6))
     x = ti.lact_inputs(cfg)
     g = {k: v.cuda() for k, v in x.items()}
     rates = np.random.default_rng(24).uniform(0.2, 1.2, size=(cfg.batch, cfg.heads, cfg.seq_len))
@@ -148,8 +150,10 @@ def test_lact_update_variants(dtype, order, variant):
         okw["eta_tok"] = kw["eta_tok"].double().cpu().numpy()      # the rates the kernel sees (fp32)
     if variant in ("dot", "all"):
         kw["loss"] = okw["loss"] = "dot"
-    if variant in ("weight_norm", "all"):
+    if variant in ("weight_norm", "all", "muon_weight_norm"):
         kw["weight_norm"] = okw["weight_norm"] = True
+    if variant.startswith("muon"):
+        kw["muon"] = okw["use_muon"] = True
     if variant == "all":
         kw["update_mask"] = okw["update_mask"] = [1, 0, 1, 1]
     got = cw.ttt_lact_swiglu(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta, cfg.order, **kw)
@@ -164,7 +168,7 @@ def test_lact_update_variants(dtype, order, variant):
         errs[name] = rel(f64(t), want)
         errs[name + "_delta"] = rel(f64(t) - w0, want - w0)
     assert all(e < tol for e in errs.values()), errs
-    if variant in ("weight_norm", "all"):
+    if variant in ("weight_norm", "all", "muon_weight_norm"):
         for t in got[1:]:
             assert torch.allclose(t.norm(dim=-1), torch.ones((), device=t.device), atol=1e-5)
 

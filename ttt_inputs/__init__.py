@@ -108,6 +108,7 @@ class LactConfig:
     loss: str = "mse"             # "mse" or "dot" (the dot-product loss -f(k)^T v)
     weight_norm: bool = False     # L2-normalise the weight rows after every update
     token_rates: bool = False     # draw per-token learning rates eta_tok ~ U(0, 1) (fp32)
+    muon: bool = False            # the Muon update rule (Newton-Schulz orthogonalised gradients)
 
     @property
     def tokens(self) -> int:
@@ -130,7 +131,12 @@ class LactConfig:
         mask = self.update_mask()
         upd = 1.0 if mask is None else sum(mask) / len(mask)
         key = 14.0 - (2.0 if self.loss == "dot" else 0.0)     # the dot loss needs no key output f(k)
-        return float(self.tokens) * self.heads * (6.0 + key * upd) * self.head_dim * self.hidden
+        total = float(self.tokens) * self.heads * (6.0 + key * upd) * self.head_dim * self.hidden
+        if self.muon:   # per updating chunk and head, 3 gradients x 5 steps of A = X X^T, A^2 and B X on [r, c]
+            r, c = min(self.head_dim, self.hidden), max(self.head_dim, self.hidden)
+            n_upd = self.n_chunks * upd
+            total += self.batch * self.heads * n_upd * 3 * 5 * (2.0 * r * r * c + 2.0 * r ** 3 + 2.0 * r * r * c)
+        return total
 
     def with_(self, **kw) -> "LactConfig":
         return replace(self, **kw)
@@ -156,6 +162,9 @@ WORKLOADS = {
     # the LaCT review's own update: dot-product loss, per-token learning rates, L2 weight normalisation
     "lact_bf16_256k_paper": LactConfig("lact_bf16_256k_paper", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
                                        loss="dot", weight_norm=True, token_rates=True),
+    # the same with the Muon update rule (L2-Normalize(W - Muon(g)))
+    "lact_bf16_256k_muon": LactConfig("lact_bf16_256k_muon", 1, 4, 262144, 512, 1024, 4096, 0.05, seed=1004,
+                                      loss="dot", weight_norm=True, token_rates=True, muon=True),
     # the same with the update on every other chunk only (a strided block-wise mask)
     "lact_bf16_256k_strided": LactConfig("lact_bf16_256k_strided", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
                                          update_every=2),
