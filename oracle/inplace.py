@@ -46,7 +46,7 @@ import numpy as np
 __all__ = [
     "silu", "causal_depthwise_conv1d", "forward_chunk_conv1d", "target_values", "gated_intermediate",
     "gated_mlp", "loss_dot", "loss_mse", "grad_dot", "grad_mse",
-    "chunk_apply_update", "chunk_prefix_form", "inplace_layer",
+    "chunk_apply_update", "chunk_core_backward", "chunk_prefix_form", "inplace_layer",
 ]
 
 
@@ -169,6 +169,37 @@ def chunk_apply_update(Z, Vhat, W0, chunk, eta, mode):
         O[rows] = Z[rows] @ W.T                       # apply: state before this chunk
         W = W - eta * grad(W, Z[rows], Vhat[rows])     # update: gradient at that state
     return O, W
+
+
+def chunk_core_backward(Z, Vhat, W0, chunk, eta, dO):
+    """Gradients of a loss through the dot-objective chunk loop (chunk_apply_update
+    with mode "dot"), given dO = dLoss/dO: returns (dZ [n, f], dVhat [n, d],
+    dW0 [d, f]).  The chain rule through O_c = Z_c W_c^T (eq. (3)) and
+    W_c = W0 + eta sum_{j<c} Vhat_j^T Z_j (eq. (6), Method §3): chunk c's output
+    gives the state gradient dW_c = dO_c^T Z_c; each delta j reaches every later
+    state, so with the exclusive suffix S_j = sum_{c>j} dW_c,
+      dZ_j    = dO_j W_j + eta Vhat_j S_j,
+      dVhat_j = eta Z_j S_j^T,
+      dW0     = sum_c dW_c.
+    The loss is taken to depend on O only (not on W_final)."""
+    Z, Vhat, W0, dO = _f64(Z), _f64(Vhat), _f64(W0), _f64(dO)
+    n = Z.shape[0]
+    bounds = [(s, min(s + chunk, n)) for s in range(0, n, chunk)]
+    states = []                                   # W_c, the state chunk c is applied with
+    W = W0.copy()
+    for (s, e) in bounds:
+        states.append(W)
+        W = W + eta * (Vhat[s:e].T @ Z[s:e])
+    dWc = [dO[s:e].T @ Z[s:e] for (s, e) in bounds]
+    dZ = np.empty_like(Z)
+    dV = np.empty_like(Vhat)
+    S = np.zeros_like(W0)                         # sum of dW_c over the chunks after the current one
+    for c in range(len(bounds) - 1, -1, -1):
+        s, e = bounds[c]
+        dZ[s:e] = dO[s:e] @ states[c] + eta * (Vhat[s:e] @ S)
+        dV[s:e] = eta * (Z[s:e] @ S.T)
+        S = S + dWc[c]
+    return dZ, dV, S
 
 
 def chunk_prefix_form(Z, Vhat, W0, chunk, eta):

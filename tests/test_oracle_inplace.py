@@ -522,3 +522,45 @@ def test_resume_rows_with_their_own_states(mode):
     np.testing.assert_array_equal(O3[0], O2[0])
     np.testing.assert_allclose(O3[1], O4[0], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(W3[1], W4[0], rtol=1e-12, atol=1e-12)
+
+
+def _torch_dot_chunk_loop(Z, V, W0, C, eta):
+    """The dot-objective chunk loop in torch float64 (apply, then update), for autograd."""
+    W = W0
+    outs = []
+    for s in range(0, Z.shape[0], C):
+        outs.append(Z[s:s + C] @ W.T)
+        W = W + eta * (V[s:s + C].T @ Z[s:s + C])
+    return torch.cat(outs)
+
+
+@pytest.mark.parametrize("n,C", [(12, 4), (10, 3), (8, 8)])
+def test_core_backward_matches_autograd(n, C):
+    """The backward of the dot chunk loop against torch autograd of the same loop in float64, for a random
+    upstream dO; includes a ragged last chunk and a single chunk."""
+    rng = _rng(50)
+    d, f, eta = 3, 5, 0.3
+    Z, V, W0, dO = (rng.standard_normal(s) for s in ((n, f), (n, d), (d, f), (n, d)))
+    dZ, dV, dW0 = orc.chunk_core_backward(Z, V, W0, C, eta, dO)
+    tz, tv, tw = (torch.tensor(a, requires_grad=True) for a in (Z, V, W0))
+    (_torch_dot_chunk_loop(tz, tv, tw, C, eta) * torch.from_numpy(dO)).sum().backward()
+    grad = lambda t: np.zeros(t.shape) if t.grad is None else t.grad.numpy()   # one chunk: V^ reaches no output
+    np.testing.assert_allclose(dZ, grad(tz), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dV, grad(tv), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dW0, grad(tw), rtol=1e-12, atol=1e-12)
+
+
+def test_core_backward_finite_differences():
+    """Central differences of <O, dO> for a few entries of Z, V^ and W0."""
+    rng = _rng(51)
+    n, C, d, f, eta = 9, 3, 2, 3, 0.4
+    Z, V, W0, dO = (rng.standard_normal(s) for s in ((n, f), (n, d), (d, f), (n, d)))
+    dZ, dV, dW0 = orc.chunk_core_backward(Z, V, W0, C, eta, dO)
+    L = lambda Z_, V_, W_: float(np.sum(orc.chunk_apply_update(Z_, V_, W_, C, eta, "dot")[0] * dO))
+    h = 1e-6
+    for arr, grad, which in ((Z, dZ, 0), (V, dV, 1), (W0, dW0, 2)):
+        for idx in [(0, 0), tuple(s - 1 for s in arr.shape), (arr.shape[0] // 2, 1)]:
+            p, m = [Z.copy(), V.copy(), W0.copy()], [Z.copy(), V.copy(), W0.copy()]
+            p[which][idx] += h
+            m[which][idx] -= h
+            assert abs((L(*p) - L(*m)) / (2 * h) - grad[idx]) < 1e-6 * max(1.0, abs(grad[idx]))
