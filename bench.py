@@ -10,7 +10,9 @@ generators of ttt_inputs), inputs resident in HBM before the timed region:
                    step entry points so that each kernel is bracketed by HIP
                    events on the launch stream;
   In-Place (mse):  ttt_chunk_apply_update (producers + in-order scan);
-  LaCT:            ttt_lact_swiglu.
+  LaCT:            ttt_lact_swiglu;
+  backward:        ttt_core_backward (gradients of Z, V^ and W_down0 through
+                   the dot chunk loop, given dLoss/dO).
 Prints one JSON line.  The CPU baseline is the float64 oracle timed on a
 bounded prefix of the same workload (whole chunks), on the host's cores.
 """
@@ -137,13 +139,25 @@ def bench_inplace_dot(cfg, steps, warmup):
 
 
 def bench_generic(cfg, steps, warmup):
-    """Whole-call timing (MSE In-Place or LaCT)."""
+    """Whole-call timing (MSE In-Place, the dot layer's variants, the backward, or LaCT)."""
     import torch
 
     import chunk_wise_weight_amd as cw
     import ttt_inputs as ti
 
-    if isinstance(cfg, ti.LactConfig):
+    if getattr(cfg, "backward", False):
+        x = ti.backward_inputs(cfg)
+        g = {k: v.cuda() for k, v in x.items()}
+        B, n, d, f = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff
+        dt = g["Z"].dtype
+        dZ = torch.empty(B, n, f, dtype=dt, device="cuda")
+        dV = torch.empty(B, n, d, dtype=dt, device="cuda")
+        dW0 = torch.empty(d, f, dtype=torch.float32, device="cuda")
+        shape = cw.InplaceShape(B, n, d, f, cfg.chunk, 1)
+        ws = torch.empty(max(1, cw.ttt_core_backward_workspace_bytes(shape, dt)), dtype=torch.uint8, device="cuda")
+        call = lambda: cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta, dZ, dV,
+                                            dW0, ws)
+    elif isinstance(cfg, ti.LactConfig):
         x = ti.lact_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
         call = lambda: cw.ttt_lact_swiglu(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta,
@@ -206,6 +220,11 @@ def cpu_baseline(cfg, target_s):
                                                    if cfg.token_rates else None),
                                           loss=cfg.loss, weight_norm=cfg.weight_norm, use_muon=cfg.muon)
         per_tok_heads = 1
+    elif cfg.backward:
+        x = ti.backward_inputs(cfg)
+        W0 = ti.to_f64(x["W_down0"])
+        run = lambda kc: orc.chunk_core_backward(*(ti.to_f64(x[k][0, : kc * cfg.chunk]) for k in ("Z", "Vhat")), W0,
+                                                 cfg.chunk, cfg.eta, ti.to_f64(x["dO"][0, : kc * cfg.chunk]))
     else:
         x = ti.inplace_inputs(cfg)
         ws = {k: ti.to_f64(x[k]) for k in ("W_gate", "W_up", "W_down0", "W_target", "conv_w")}
@@ -286,9 +305,12 @@ def main():
             out["config"]["conv"] = "forward in-chunk"
         if cfg.pieces > 1:
             out["config"]["calls_per_sequence"] = cfg.pieces
+        if cfg.backward:
+            out["config"]["pass"] = "backward of the chunk loop (dZ, dVhat, dW_down0 from dLoss/dO)"
+            out["metric"] = "TTT chunk-loop backward tokens/s at 128K ctx; % of bf16 MFMA peak"
 
     if (not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot" and cfg.docs == 1 and not cfg.conv_forward and
-            cfg.pieces == 1):
+            cfg.pieces == 1 and not cfg.backward):
         wall, per, _ = bench_inplace_dot(cfg, args.steps, args.warmup)
         fl, by = kernel_flops(cfg), kernel_bytes(cfg, 2 if dtype == "bf16" else 4)
         kern = {}

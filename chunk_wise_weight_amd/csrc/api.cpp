@@ -164,7 +164,7 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
     if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, df, eta, p.docs, p.Winit, s));
   }
   if (st != TTT_OK) return st;
-  return dev(ttt::launch_apply<T>(Zt, Wc, (int64_t)k * df, df, O, B, n, d, f, C, s));
+  return dev(ttt::launch_apply<T>(Zt, Wc, (int64_t)k * df, df, O, B, n, d, f, C, 1.0f, s));
 }
 
 // Zt and Vt from the producers' inputs.
@@ -179,7 +179,7 @@ int run_producers(const Plan& p, const void* H, const void* X0, const void* Wg, 
   int st = dev(ttt::launch_produce_z<T>((const T*)H, (const T*)Wg, (const T*)Wu, nullptr, Zt, rows, n, d, f, s));
   if (st == TTT_OK) st = dev(ttt::launch_conv<T>((const T*)X0, (const T*)cw, Y, rows, n, d, (int)p.K, p.docs, (int)p.C,
                                                   p.conv_fwd, (const T*)p.halo, s));
-  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Wt, WtT, 1, d, d, 1.0f, s));
+  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Wt, WtT, 1, d, d, 1.0f, 0, s));
   if (st == TTT_OK) st = dev(ttt::launch_produce_vhat<T>(Y, WtT, Vt, rows, n, d, vscale, s));
   return st;
 }
@@ -207,11 +207,120 @@ int core(const Plan& p, int mode, float eta, const void* Z, const void* V, const
          char* ws, hipStream_t s) {
   T* Zt = (T*)(ws + p.off_Zt);
   T* Vt = (T*)(ws + p.off_Vt);
-  int st = dev(ttt::launch_transpose<T>((const T*)Z, Zt, (int)p.B, (int)p.n, (int)p.f, 1.0f, s));
+  int st = dev(ttt::launch_transpose<T>((const T*)Z, Zt, (int)p.B, (int)p.n, (int)p.f, 1.0f, 0, s));
   if (st == TTT_OK)
-    st = dev(ttt::launch_transpose<T>((const T*)V, Vt, (int)p.B, (int)p.n, (int)p.d, target_scale(p, mode, eta), s));
+    st = dev(ttt::launch_transpose<T>((const T*)V, Vt, (int)p.B, (int)p.n, (int)p.d, target_scale(p, mode, eta), 0,
+                                      s));
   if (st != TTT_OK) return st;
   return run_core<T>(p, mode, eta, Zt, Vt, W0, O, Wf, ws, s);
+}
+
+// ------------------------------------------------------------------ backward of the dot chunk loop
+
+// Workspace of ttt_core_backward: the token-contiguous operands of the two
+// scans (Z and eta V^ in order, Z and dO with the chunk order reversed), the
+// forward states W_c and reversed suffix states S, the per-row totals, a zero
+// [d, f] start state, and the scans' own scratch (segment partials, or the
+// per-chunk deltas when the chunk length does not suit the fused scan).
+struct BwdPlan {
+  int64_t B, n, d, f, C, k;
+  size_t esz;
+  bool fused;
+  int S;
+  size_t off_Zt, off_Vt, off_Zr, off_Gr, off_Wc, off_Sr, off_T, off_zero, off_Wp, off_Tot, off_dW, total;
+};
+
+int make_bwd_plan(const ttt_inplace_shape* s, int dtype, BwdPlan* p) {
+  int st = check_inplace_shape(s, dtype);
+  if (st != TTT_OK) return st;
+  memset(p, 0, sizeof(*p));
+  p->B = s->batch;
+  p->n = s->seq_len;
+  p->d = s->d_model;
+  p->f = s->d_ff;
+  p->C = s->chunk;
+  p->k = s->seq_len / s->chunk;
+  p->esz = dtype == TTT_BF16 ? 2 : 4;
+  p->fused = p->C % kstep(dtype) == 0;
+  p->S = p->fused ? ttt::update_scan_segments(p->d, p->f, p->k, p->C) : 1;
+  if (p->B * p->n == 0) return TTT_OK;      // nothing but a zero dW_down0
+  const size_t BN = (size_t)p->B * p->n, DF = (size_t)p->d * p->f, BK = (size_t)p->B * p->k;
+  size_t off = 0;
+  auto take = [&](size_t* o, size_t bytes) {
+    *o = off;
+    off += align_up(bytes);
+  };
+  take(&p->off_Zt, BN * p->f * p->esz);
+  take(&p->off_Vt, BN * p->d * p->esz);
+  take(&p->off_Zr, BN * p->f * p->esz);
+  take(&p->off_Gr, BN * p->d * p->esz);
+  take(&p->off_Wc, BK * DF * p->esz);
+  take(&p->off_Sr, BK * DF * p->esz);
+  take(&p->off_T, (size_t)p->B * DF * 4);
+  take(&p->off_zero, DF * p->esz);
+  if (p->fused && p->S > 1) {
+    take(&p->off_Wp, (size_t)p->B * (p->k - p->k / p->S) * DF * p->esz);
+    take(&p->off_Tot, (size_t)p->B * (p->S - 1) * DF * 4);
+  } else if (!p->fused) {
+    take(&p->off_dW, BK * DF * 4);
+  }
+  p->total = off;
+  return TTT_OK;
+}
+
+// One exclusive scan over the chunks of (Zt, Vt) from W0 into the states Wc and
+// the total Wf: the fused update-scan (Vt already scaled by eta), or deltas and
+// a scan with eta.
+template <typename T>
+int bwd_scan(const BwdPlan& p, const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, float eta, char* ws,
+             hipStream_t s) {
+  const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
+  if (p.fused)
+    return dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (T*)(ws + p.off_Wp), (float*)(ws + p.off_Tot), B,
+                                                n, d, f, C, p.S, nullptr, nullptr, s));
+  float* dW = (float*)(ws + p.off_dW);
+  int st = dev(ttt::launch_chunk_delta<T>(Zt, Vt, dW, B, n, d, f, C, s));
+  if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, (int64_t)d * f, eta, nullptr, nullptr, s));
+  return st;
+}
+
+// The backward pass: both scans, then dV^ as an apply of the suffix states (in
+// reverse chunk order, by a negative state stride) and dZ from both state
+// sequences, and dW_down0 as the sum of the rows' totals.
+template <typename T>
+int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, const void* W0, const void* dOv,
+                  void* dZ, void* dV, float* dW0, char* ws, hipStream_t s) {
+  const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
+  const int64_t df = (int64_t)d * f;
+  if (p.B * p.n == 0) return dev(ttt::launch_zero<float>(dW0, df, s));
+  const T* Z = (const T*)Zv;
+  const T* V = (const T*)Vv;
+  const T* dO = (const T*)dOv;
+  T* Zt = (T*)(ws + p.off_Zt);
+  T* Vt = (T*)(ws + p.off_Vt);
+  T* Zr = (T*)(ws + p.off_Zr);
+  T* Gr = (T*)(ws + p.off_Gr);
+  T* Wc = (T*)(ws + p.off_Wc);
+  T* Sr = (T*)(ws + p.off_Sr);
+  T* Z0 = (T*)(ws + p.off_zero);
+  float* Tt = (float*)(ws + p.off_T);
+  const T* Slast = Sr + (int64_t)(k - 1) * df;      // S_c = Sr[k - 1 - c]: stride -df from here
+  int st = dev(ttt::launch_transpose<T>(Z, Zt, B, n, f, 1.0f, 0, s));
+  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(V, Vt, B, n, d, p.fused ? eta : 1.0f, 0, s));
+  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zr, B, n, f, 1.0f, C, s));
+  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(dO, Gr, B, n, d, 1.0f, C, s));
+  if (st == TTT_OK) st = dev(ttt::launch_zero<T>(Z0, df, s));
+  // W_c (its W_final lands in Tt and is overwritten by the second scan)
+  if (st == TTT_OK) st = bwd_scan<T>(p, Zt, Vt, (const T*)W0, Wc, Tt, eta, ws, s);
+  // reversed order: Sr[t] = sum of dO_c^T Z_c over the chunks c > k - 1 - t; Tt = all chunks
+  if (st == TTT_OK) st = bwd_scan<T>(p, Zr, Gr, Z0, Sr, Tt, 1.0f, ws, s);
+  if (st == TTT_OK)
+    st = dev(ttt::launch_apply<T>(Zt, Slast, (int64_t)k * df, -df, (T*)dV, B, n, d, f, C, eta, s));
+  if (st == TTT_OK)
+    st = dev(ttt::launch_dz<T>(dO, V, Wc, (int64_t)k * df, df, Slast, (int64_t)k * df, -df, (T*)dZ, B, n, d, f, C,
+                               eta, s));
+  if (st == TTT_OK) st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
+  return st;
 }
 
 }  // namespace
@@ -312,6 +421,34 @@ int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, f
   return core<float>(p, mode, eta, Z, Vhat, W_down0, O, W_final, (char*)workspace, s);
 }
 
+int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_ARG;
+  BwdPlan p;
+  int st = make_bwd_plan(shape, dtype, &p);
+  if (st != TTT_OK) return st;
+  *bytes = p.total;
+  return TTT_OK;
+}
+
+int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
+                      const void* W_down0, const void* dO, void* dZ, void* dVhat, float* dW_down0, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  BwdPlan p;
+  int st = make_bwd_plan(shape, dtype, &p);
+  if (st != TTT_OK) return st;
+  if (!finite(eta)) return TTT_ERR_ARG;
+  if (!ok_ptr(dW_down0)) return TTT_ERR_ARG;
+  if (p.B * p.n > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(W_down0) || !ok_ptr(dO) || !ok_ptr(dZ) ||
+                        !ok_ptr(dVhat)))
+    return TTT_ERR_ARG;
+  if (p.total > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < p.total))
+    return TTT_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == TTT_BF16)
+    return core_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, dZ, dVhat, dW_down0, (char*)workspace, s);
+  return core_backward<float>(p, eta, Z, Vhat, W_down0, dO, dZ, dVhat, dW_down0, (char*)workspace, s);
+}
+
 int ttt_produce_z(const ttt_inplace_shape* shape, int dtype, const void* H, const void* W_gate, const void* W_up,
                   void* Z, void* Zt, void* stream) {
   int st = check_inplace_shape(shape, dtype);
@@ -364,7 +501,7 @@ int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, float scale, con
     st = dev(ttt::launch_conv<bf16>((const bf16*)X0, (const bf16*)conv_w, (bf16*)(ws + p.off_Y), rows, n, d, K, nullptr,
                                     (int)p.C, false, nullptr, s));
     if (st == TTT_OK)
-      st = dev(ttt::launch_transpose<bf16>((const bf16*)W_target, (bf16*)(ws + p.off_WtT), 1, d, d, 1.0f, s));
+      st = dev(ttt::launch_transpose<bf16>((const bf16*)W_target, (bf16*)(ws + p.off_WtT), 1, d, d, 1.0f, 0, s));
     if (st == TTT_OK)
       st = dev(ttt::launch_produce_vhat<bf16>((const bf16*)(ws + p.off_Y), (const bf16*)(ws + p.off_WtT), (bf16*)Vt,
                                               rows, n, d, scale, s));
@@ -373,7 +510,7 @@ int ttt_produce_vhat(const ttt_inplace_shape* shape, int dtype, float scale, con
   st = dev(ttt::launch_conv<float>((const float*)X0, (const float*)conv_w, (float*)(ws + p.off_Y), rows, n, d, K,
                                    nullptr, (int)p.C, false, nullptr, s));
   if (st == TTT_OK)
-    st = dev(ttt::launch_transpose<float>((const float*)W_target, (float*)(ws + p.off_WtT), 1, d, d, 1.0f, s));
+    st = dev(ttt::launch_transpose<float>((const float*)W_target, (float*)(ws + p.off_WtT), 1, d, d, 1.0f, 0, s));
   if (st == TTT_OK)
     st = dev(ttt::launch_produce_vhat<float>((const float*)(ws + p.off_Y), (const float*)(ws + p.off_WtT),
                                              (float*)Vt, rows, n, d, scale, s));
@@ -476,8 +613,10 @@ int ttt_chunk_apply(const ttt_inplace_shape* shape, int dtype, const void* Zt, c
             C = (int)shape->chunk;
   const int64_t df = (int64_t)d * f, k = n / C;
   if (dtype == TTT_BF16)
-    return dev(ttt::launch_apply<bf16>((const bf16*)Zt, (const bf16*)Wc, k * df, df, (bf16*)O, B, n, d, f, C, s));
-  return dev(ttt::launch_apply<float>((const float*)Zt, (const float*)Wc, k * df, df, (float*)O, B, n, d, f, C, s));
+    return dev(
+        ttt::launch_apply<bf16>((const bf16*)Zt, (const bf16*)Wc, k * df, df, (bf16*)O, B, n, d, f, C, 1.0f, s));
+  return dev(
+      ttt::launch_apply<float>((const float*)Zt, (const float*)Wc, k * df, df, (float*)O, B, n, d, f, C, 1.0f, s));
 }
 
 // ------------------------------------------------------------------ LaCT

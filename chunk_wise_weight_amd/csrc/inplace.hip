@@ -112,9 +112,11 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
 }
 
 // dst[b][c][r] = scale * src[b][r][c] for an R x C matrix per batch entry (64 x 64 tiles).
+// rev > 0: the rows come in blocks of rev (chunks) whose order is reversed in
+// dst, i.e. r lands at column (R / rev - 1 - r / rev) rev + r % rev.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, T* __restrict__ dst, int R, int C,
-                                                   float scale) {
+                                                   float scale, int rev) {
   __shared__ T tile[64][65];
   const int64_t b = blockIdx.y;
   const int tc = (C + 63) / 64;
@@ -129,7 +131,8 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, T*
   __syncthreads();
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
-    if (c < C && r < R) o[(int64_t)c * R + r] = scale == 1.0f ? tile[tx][i] : from_f32<T>(scale * to_f32(tile[tx][i]));
+    const int rr = rev > 0 ? (R / rev - 1 - r / rev) * rev + r % rev : r;
+    if (c < C && r < R) o[(int64_t)c * R + rr] = scale == 1.0f ? tile[tx][i] : from_f32<T>(scale * to_f32(tile[tx][i]));
   }
 }
 
@@ -537,7 +540,7 @@ __global__ __launch_bounds__(256) void k_scan_fixup(T* __restrict__ Wc, const T*
 // over) as an MN-major operand, so no row-major copy of Z is needed.
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict__ W, int64_t wsb, int64_t wsc,
-                                   T* __restrict__ O, int n, int d, int f, int C_) {
+                                   T* __restrict__ O, int n, int d, int f, int C_, float oscale) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
@@ -572,7 +575,9 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
       const int q = G::acc_q(j) - ps * RPP;
       if (q < 0 || q >= RPP) continue;
 #pragma unroll
-      for (int i = 0; i < G::NPB; ++i) st.put4(q, G::acc_p(i, 0), acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      for (int i = 0; i < G::NPB; ++i)
+        st.put4(q, G::acc_p(i, 0), oscale * acc[i][j][0], oscale * acc[i][j][1], oscale * acc[i][j][2],
+                oscale * acc[i][j][3]);
     }
     __syncthreads();
     st.template flush<G::NT>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
@@ -580,6 +585,91 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
     });
     __syncthreads();
   }
+}
+
+// ------------------------------------------------------------------ backward of the dot chunk loop
+
+// dZ_j = dO_j W_j + eta V^_j S_j for every chunk j, with W_j the state chunk j
+// was applied with and S_j = sum_{c>j} dO_c^T Z_c (Method §3's prefix form
+// differentiated; see the backward entry point).  P = d_ff columns of the
+// [d, f] states (MN-major: f contiguous), Q = the chunk's tokens (rows of V^ and
+// dO, [n, d]), K = d_model: one K loop over (S_j, V^_j), the accumulator scaled
+// by eta, a second over (W_j, dO_j).  State j sits at W + b wsb + j wsc (S
+// likewise; its stride may be negative).  dZ [B, n, f] through LDS like O.
+template <typename T>
+TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ V, const T* __restrict__ W,
+                                int64_t wsb, int64_t wsc, const T* __restrict__ S, int64_t ssb, int64_t ssc,
+                                T* __restrict__ dZ, int n, int d, int f, int C_, float eta) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (f + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
+  const int per = TP * TQ;
+  const int id = group_sync_tile(blockIdx.x, gridDim.x, per);     // all XCDs on one chunk at a time
+  const int bc = id / per;
+  int tp, tq;
+  grouped_tile(id - bc * per, TP, TQ, 4, tp, tq);
+  const int k = n / C_;
+  const int b = bc / k, c = bc - b * k;
+  const int j0 = tp * G::BP, t0 = tq * G::BQ;
+  const int64_t row0 = (int64_t)b * n + (int64_t)c * C_ + t0;
+  const uint64_t ldd = (uint64_t)d * esz<T>(), ldf = (uint64_t)f * esz<T>();
+  constexpr int KR = DmaOpMN<T, G::NW, G::BP>::KR;
+  const int nks = (d + KR - 1) / KR;
+  typename G::Frag acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  {
+    DmaOpMN<T, G::NW, G::BP> op;
+    DmaOp<G::NW, G::BQ> oq;
+    op.init(S + (int64_t)b * ssb + (int64_t)c * ssc + j0, min(G::BP, f - j0), ldf, d);
+    oq.init(V + row0 * d, nullptr, min(G::BQ, C_ - t0), ldd, (unsigned)ldd);
+    mainloop<T, G>(op, oq, nks, acc, smem, NoHook{});
+  }
+#pragma unroll
+  for (int i = 0; i < G::NPB; ++i)
+#pragma unroll
+    for (int j = 0; j < G::NQB; ++j) acc[i][j] *= eta;
+  {
+    DmaOpMN<T, G::NW, G::BP> op;
+    DmaOp<G::NW, G::BQ> oq;
+    op.init(W + (int64_t)b * wsb + (int64_t)c * wsc + j0, min(G::BP, f - j0), ldf, d);
+    oq.init(dO + row0 * d, nullptr, min(G::BQ, C_ - t0), ldd, (unsigned)ldd);
+    mainloop<T, G>(op, oq, nks, acc, smem, NoHook{});
+  }
+  const int tn = min(G::BQ, C_ - t0), jn = min(G::BP, f - j0);
+  constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
+  const Staged<T, G::BP> st{smem};
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+#pragma unroll
+    for (int j = 0; j < G::NQB; ++j) {
+      const int q = G::acc_q(j) - ps * RPP;
+      if (q < 0 || q >= RPP) continue;
+#pragma unroll
+      for (int i = 0; i < G::NPB; ++i) st.put4(q, G::acc_p(i, 0), acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+    }
+    __syncthreads();
+    st.template flush<G::NT>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
+      return col < jn ? dZ + (row0 + ps * RPP + r) * f + j0 + col : nullptr;
+    });
+    __syncthreads();
+  }
+}
+
+// out = sum over the B rows of Tot [B, df] (fp32), four elements per thread.
+__global__ __launch_bounds__(256) void k_sum_rows(const float* __restrict__ Tot, float* __restrict__ out, int B,
+                                                  int64_t df) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= df) return;
+  f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < B; ++b) s += load4(Tot + (int64_t)b * df + e);
+  store4(out + e, s[0], s[1], s[2], s[3]);
+}
+
+// p[0 .. n) = 0, four elements per thread (n % 4 == 0).
+template <typename T>
+__global__ __launch_bounds__(256) void k_zero(T* __restrict__ p, int64_t n) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e < n) store4(p + e, 0.f, 0.f, 0.f, 0.f);
 }
 
 // ------------------------------------------------------------------ MSE objective
@@ -755,9 +845,10 @@ hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int 
 }
 
 template <typename T>
-hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int Cs, float scale, hipStream_t s) {
+hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int Cs, float scale, int rev, hipStream_t s) {
   if (batch == 0 || R == 0 || Cs == 0) return hipSuccess;
-  k_transpose<T><<<dim3((unsigned)(cdiv(Cs, 64) * cdiv(R, 64)), (unsigned)batch), 256, 0, s>>>(src, dst, R, Cs, scale);
+  k_transpose<T><<<dim3((unsigned)(cdiv(Cs, 64) * cdiv(R, 64)), (unsigned)batch), 256, 0, s>>>(src, dst, R, Cs, scale,
+                                                                                             rev);
   return hipGetLastError();
 }
 
@@ -812,10 +903,32 @@ hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc
 
 template <typename T>
 hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int Cs,
-                        hipStream_t s) {
+                        float oscale, hipStream_t s) {
   const int64_t tiles = cdiv(d, kWB) * cdiv(Cs, kWB) * B * (n / Cs);
   if (tiles == 0) return hipSuccess;
-  k_apply<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, W, wsb, wsc, O, n, d, f, Cs);
+  k_apply<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, W, wsb, wsc, O, n, d, f, Cs, oscale);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dz(const T* dO, const T* V, const T* W, int64_t wsb, int64_t wsc, const T* S, int64_t ssb,
+                     int64_t ssc, T* dZ, int B, int n, int d, int f, int Cs, float eta, hipStream_t s) {
+  const int64_t tiles = cdiv(f, kWB) * cdiv(Cs, kWB) * B * (n / Cs);
+  if (tiles == 0) return hipSuccess;
+  k_dz<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(dO, V, W, wsb, wsc, S, ssb, ssc, dZ, n, d, f, Cs, eta);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_rows(const float* Tot, float* out, int B, int64_t df, hipStream_t s) {
+  if (df == 0) return hipSuccess;
+  k_sum_rows<<<(unsigned)cdiv(df / 4, 256), 256, 0, s>>>(Tot, out, B, df);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_zero(T* p, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_zero<T><<<(unsigned)cdiv(n / 4, 256), 256, 0, s>>>(p, n);
   return hipGetLastError();
 }
 
@@ -855,7 +968,7 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
 #define TTT_INST(T)                                                                                               \
   template hipError_t launch_conv<T>(const T*, const T*, T*, int64_t, int, int, int, const uint8_t*, int, bool,  \
                                      const T*, hipStream_t);                                                      \
-  template hipError_t launch_transpose<T>(const T*, T*, int, int, int, float, hipStream_t);                      \
+  template hipError_t launch_transpose<T>(const T*, T*, int, int, int, float, int, hipStream_t);                 \
   template hipError_t launch_produce_z<T>(const T*, const T*, const T*, T*, T*, int64_t, int, int, int,          \
                                           hipStream_t);                                                           \
   template hipError_t launch_produce_vhat<T>(const T*, const T*, T*, int64_t, int, int, float, hipStream_t);     \
@@ -865,8 +978,11 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
   template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, T*, float*, int,      \
                                                   int, int, int, int, int, const uint8_t*, const float*,          \
                                                   hipStream_t);                                                   \
-  template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int,          \
+  template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int, float,   \
                                       hipStream_t);                                                               \
+  template hipError_t launch_dz<T>(const T*, const T*, const T*, int64_t, int64_t, const T*, int64_t, int64_t, T*, \
+                                   int, int, int, int, int, float, hipStream_t);                                  \
+  template hipError_t launch_zero<T>(T*, int64_t, hipStream_t);                                                   \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
                                           const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t); \
   template hipError_t launch_state_copy<T>(const float*, float*, T*, int, int64_t, hipStream_t);

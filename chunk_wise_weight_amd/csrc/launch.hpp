@@ -12,7 +12,7 @@ template <typename T>
 hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, const uint8_t* docs, int C,
                        bool fwd, const T* halo, hipStream_t s);
 template <typename T>
-hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int C, float scale, hipStream_t s);
+hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int C, float scale, int rev, hipStream_t s);
 template <typename T>
 hipError_t launch_produce_z(const T* H, const T* Wg, const T* Wu, T* Z, T* Zt, int64_t rows, int n, int d, int f,
                             hipStream_t s);
@@ -54,7 +54,17 @@ inline int update_scan_segments(int64_t d, int64_t f, int64_t k, int64_t C) {
 }
 template <typename T>
 hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
-                        hipStream_t s);
+                        float oscale, hipStream_t s);
+// dZ_c = dO_c W_c + eta V_c S_c per chunk (backward of the dot chunk loop);
+// states W_c at W + b wsb + c wsc and S_c at S + b ssb + c ssc, [d, f] each.
+template <typename T>
+hipError_t launch_dz(const T* dO, const T* V, const T* W, int64_t wsb, int64_t wsc, const T* S, int64_t ssb,
+                     int64_t ssc, T* dZ, int B, int n, int d, int f, int C, float eta, hipStream_t s);
+// out [df] = sum over b of Tot [B, df] (fp32; df % 4 == 0).
+hipError_t launch_sum_rows(const float* Tot, float* out, int B, int64_t df, hipStream_t s);
+// p [n] = 0 (n % 4 == 0).
+template <typename T>
+hipError_t launch_zero(T* p, int64_t n, hipStream_t s);
 template <typename T>
 hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
                             T* Rt, const uint8_t* docs, bool cont, int B, int n, int d, int f, int C, int c,

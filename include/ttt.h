@@ -178,6 +178,37 @@ int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, f
                           void* O, float* W_final, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* ---- backward of the dot chunk loop ---- */
+
+/* Workspace bytes for ttt_core_backward: about 2 B (k d f + 2 n (d + f)) dtype
+ * elements plus B d f fp32 (the recomputed states, the suffix states and the
+ * transposed operands below). */
+int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes);
+
+/* Gradients through the dot-objective chunk loop (ttt_core_apply_update with
+ * TTT_MODE_DOT), for a loss that depends on O alone, given its gradient
+ * dO = dLoss/dO [B, n, d] (dtype).  By the chain rule through
+ * O_c = Z_c W_c^T (eq. (3)) and W_c = W_down0 + eta sum_{j<c} V^_j^T Z_j
+ * (eq. (6), prefix form of Method §3), with the exclusive suffix
+ * S_c = sum_{j>c} dO_j^T Z_j of each row:
+ *   dZ       [B, n, f] dtype:  dZ_c = dO_c W_c + eta V^_c S_c
+ *   dVhat    [B, n, d] dtype:  dV^_c = eta Z_c S_c^T
+ *   dW_down0 [d, f]    fp32:   sum over rows and chunks of dO_c^T Z_c
+ *                              (W_down0 is shared by the rows, so their
+ *                              gradients add).
+ * The states W_c are recomputed by the chunk scan; the suffixes come from the
+ * same scan run over the chunks in reverse order on (Z, dO) from a zero state,
+ * so each S_c is a sum of its own terms, never a difference of prefix sums.
+ * With bf16 the states W_c and S_c are held in bf16 (fp32 accumulation), as in
+ * the forward call.  Rows are single documents starting at W_down0 (no
+ * document starts, resumed state or update mask).  Inputs as in
+ * ttt_core_apply_update; conv_k is not used.  seq_len == 0 or batch == 0
+ * gives dW_down0 = 0 and touches nothing else.  Errors as for every entry
+ * point (a too small workspace: TTT_ERR_WORKSPACE). */
+int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
+                      const void* W_down0, const void* dO, void* dZ, void* dVhat, float* dW_down0,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- the individual steps (each is one stage of the call above; they compose
  *      into it and exist for composition and per-step checks).  The updates
  *      contract over tokens, so they read token-contiguous (transposed) copies:

@@ -193,6 +193,47 @@ def test_step_entry_points_validate():
     assert lib.ttt_chunk_apply(ctypes.byref(s), cw.TTT_BF16, _fake(), None, _fake(), None) == cw.TTT_ERR_ARG
 
 
+def test_backward_workspace_and_validation():
+    """ttt_core_backward's workspace: Z and eta V^ token-contiguous, the same two with the chunk order reversed,
+    the recomputed states and the suffix states (dtype), the rows' fp32 totals, a zero start state, and the
+    scans' own scratch (segment partials for the fused scan, fp32 deltas otherwise)."""
+    lib = cw.lib()
+    al = lambda x: (x + 255) // 256 * 256
+    out = ctypes.c_size_t(0)
+
+    def ws(B, n, d, f, C, dtype=cw.TTT_BF16):
+        st = lib.ttt_core_backward_workspace_bytes(ctypes.byref(cw.InplaceShape(B, n, d, f, C, 1)), dtype,
+                                                   ctypes.byref(out))
+        return st, out.value
+
+    B, n, d, f, C = 2, 2048, 256, 512, 256      # fused, four segments (as the forward plan of this shape)
+    k, e = n // C, 2
+    base = 2 * (al(B * n * f * e) + al(B * n * d * e)) + 2 * al(B * k * d * f * e) + al(B * d * f * 4) + al(d * f * e)
+    assert ws(B, n, d, f, C) == (cw.TTT_OK, base + al(B * (k - k // 4) * d * f * e) + al(B * 3 * d * f * 4))
+    # chunk 40: not on the 64-token step of the fused scan, so per-chunk fp32 deltas
+    n2, C2 = 2000, 40
+    k2 = n2 // C2
+    base2 = 2 * (al(B * n2 * f * e) + al(B * n2 * d * e)) + 2 * al(B * k2 * d * f * e) + al(B * d * f * 4) + \
+        al(d * f * e)
+    assert ws(B, n2, d, f, C2) == (cw.TTT_OK, base2 + al(B * k2 * d * f * 4))
+    assert ws(0, n, d, f, C) == (cw.TTT_OK, 0) and ws(B, 0, d, f, C) == (cw.TTT_OK, 0)
+    assert ws(B, 2000, d, f, C)[0] == cw.TTT_ERR_SHAPE
+    assert lib.ttt_core_backward_workspace_bytes(ctypes.byref(cw.InplaceShape(B, n, d, f, C, 1)), cw.TTT_BF16,
+                                                 None) == cw.TTT_ERR_ARG
+    s = cw.InplaceShape(B, n, d, f, C, 1)
+    nb = ws(B, n, d, f, C)[1]
+    p6 = [_fake() for _ in range(6)]   # Z, Vhat, W_down0, dO, dZ, dVhat
+    call = lambda eta, ptrs, dW, w, nbytes: lib.ttt_core_backward(ctypes.byref(s), cw.TTT_BF16, eta, *ptrs, dW, w,
+                                                                    nbytes, None)
+    assert call(0.1, p6, _fake(), _fake(), nb - 1) == cw.TTT_ERR_WORKSPACE
+    assert call(0.1, p6, _fake(), None, nb) == cw.TTT_ERR_WORKSPACE
+    assert call(float("nan"), p6, _fake(), _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, p6, None, _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, [None] + p6[1:], _fake(), _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, p6[:3] + [ctypes.c_void_p(0x100008)] + p6[4:], _fake(), _fake(), nb) == cw.TTT_ERR_ARG
+    assert lib.ttt_core_backward(ctypes.byref(s), 7, 0.1, *p6, _fake(), _fake(), nb, None) == cw.TTT_ERR_DTYPE
+
+
 def test_lact_validation():
     lib = cw.lib()
     out = ctypes.c_size_t(0)

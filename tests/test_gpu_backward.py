@@ -1,0 +1,124 @@
+"""GPU parity of the backward of the dot chunk loop (ttt_core_backward) against the float64 oracle.
+
+The oracle's chunk_core_backward is pinned on the CPU by torch autograd and central differences.  Every call goes
+through the C ABI; inputs come from the seeded generator and the oracle sees the same rounded values.  Tolerances
+(relative Frobenius): 1e-4 for fp32; 2e-2 for bf16, whose path rounds the transposed operands' scale, the recomputed
+states W_c and the suffix states S_c once each (about 2^-9 relative apiece) before the final contractions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunk_wise_weight_amd as cw
+import ttt_inputs as ti
+from oracle import inplace as orc
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def cfg_of(dtype, B, k, C, d=264, f=392, eta=0.05, seed=31):
+    return ti.InplaceConfig("bwd", B, k * C, d, f, C, eta, "dot", dtype, seed=seed, backward=True)
+
+
+def run(cfg):
+    x = ti.backward_inputs(cfg)
+    g = {name: t.cuda() for name, t in x.items()}
+    dZ, dV, dW0 = cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta)
+    torch.cuda.synchronize()
+    return x, f64(dZ), f64(dV), f64(dW0)
+
+
+def oracle(x, cfg):
+    Z, V, W0, dO = (ti.to_f64(x[name]) for name in ("Z", "Vhat", "W_down0", "dO"))
+    outs = [orc.chunk_core_backward(Z[b], V[b], W0, cfg.chunk, cfg.eta, dO[b]) for b in range(cfg.batch)]
+    return (np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]), sum(o[2] for o in outs))
+
+
+# fused scan with four segments (k = 4), one segment (k = 3), and the delta + scan path (chunk not a multiple
+# of the fused scan's K step: 40 for fp32, 72 for bf16); every case has ragged 256-tiles in d and f
+@pytest.mark.parametrize("dtype,C,k", [("f32", 96, 4), ("f32", 40, 3), ("bf16", 128, 4), ("bf16", 128, 3),
+                                       ("bf16", 72, 2)])
+def test_backward_matches_oracle(dtype, C, k):
+    cfg = cfg_of(dtype, 2, k, C)
+    x, dZ, dV, dW0 = run(cfg)
+    rZ, rV, rW = oracle(x, cfg)
+    assert rel(dZ, rZ) < TOL[dtype]
+    assert rel(dV, rV) < TOL[dtype]
+    assert rel(dW0, rW) < TOL[dtype]
+
+
+def test_backward_single_chunk():
+    # one chunk: no later chunk, so dVhat = 0 exactly and dZ = dO W_down0
+    cfg = cfg_of("bf16", 1, 1, 256)
+    x, dZ, dV, dW0 = run(cfg)
+    rZ, rV, rW = oracle(x, cfg)
+    assert not np.any(dV)
+    assert rel(dZ, rZ) < TOL["bf16"] and rel(dW0, rW) < TOL["bf16"]
+
+
+def test_backward_eta_zero():
+    # eta = 0: the states never move and no gradient reaches Vhat; dZ = dO W_down0 for every chunk
+    cfg = cfg_of("f32", 2, 3, 64, eta=0.0)
+    x, dZ, dV, dW0 = run(cfg)
+    assert not np.any(dV)
+    ref = ti.to_f64(x["dO"]) @ ti.to_f64(x["W_down0"])
+    assert rel(dZ, ref) < TOL["f32"]
+
+
+def test_backward_empty():
+    for B, n in ((0, 256), (2, 0)):
+        cfg = ti.InplaceConfig("bwd", B, n, 264, 392, 128, 0.05, "dot", "f32", backward=True)
+        x = ti.backward_inputs(cfg)
+        g = {name: t.cuda() for name, t in x.items()}
+        dW0 = torch.full((264, 392), float("nan"), device="cuda")
+        cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], 128, 0.05, dW_down0=dW0)
+        torch.cuda.synchronize()
+        assert not torch.any(dW0)
+
+
+def test_backward_rows_independent():
+    # batch rows do not interact: row 1 alone gives row 1's dZ and dVhat bits, and dW_down0 adds the rows' parts
+    cfg = cfg_of("bf16", 2, 4, 128)
+    x = ti.backward_inputs(cfg)
+    g = {name: t.cuda() for name, t in x.items()}
+    dZ, dV, dW0 = cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta)
+    one = {name: (t[1:2].contiguous() if name != "W_down0" else t) for name, t in g.items()}
+    dZ1, dV1, dW01 = cw.ttt_core_backward(one["Z"], one["Vhat"], one["W_down0"], one["dO"], cfg.chunk, cfg.eta)
+    torch.cuda.synchronize()
+    assert torch.equal(dZ[1:2], dZ1) and torch.equal(dV[1:2], dV1)
+    assert rel(f64(dW0), oracle(x, cfg)[2]) < TOL["bf16"]
+
+
+def test_full_size_backward_sampled():
+    """The 128K workload (131072 tokens, d 2560, d_ff 9728, chunk 4096).  The maps are separable: columns P of dZ
+    and dW_down0 depend on columns P of Z and W_down0 only, and the last chunks' dVhat on those chunks alone (their
+    suffixes), so the oracle runs on a column slice over the whole sequence and on the last two chunks."""
+    cfg = ti.workload("inplace_bwd_bf16_128k")
+    x, dZ, dV, dW0 = run(cfg)
+    C = cfg.chunk
+    rng = np.random.default_rng(5)
+    P = np.sort(rng.choice(cfg.d_ff, 24, replace=False))
+    Z = x["Z"][0]
+    V = ti.to_f64(x["Vhat"][0])
+    dO = ti.to_f64(x["dO"][0])
+    W0 = ti.to_f64(x["W_down0"])
+    rZ, _, rW = orc.chunk_core_backward(ti.to_f64(Z[:, P]), V, W0[:, P], C, cfg.eta, dO)
+    assert rel(dZ[0][:, P], rZ) < TOL["bf16"]
+    assert rel(dW0[:, P], rW) < TOL["bf16"]
+    t0 = cfg.seq_len - 2 * C
+    _, rV, _ = orc.chunk_core_backward(ti.to_f64(Z[t0:]), V[t0:], W0, C, cfg.eta, dO[t0:])
+    assert rel(dV[0][t0:], rV) < TOL["bf16"]
+    assert np.all(np.isfinite(dZ)) and np.all(np.isfinite(dV))

@@ -15,6 +15,9 @@ Recipe (for every workload):
     the bf16 rounding (input preparation, not part of the layer).
 
 Draw order, In-Place layer: H, X0, W_gate, W_up, W_down0, W_target, conv_w.
+Draw order, backward of the chunk loop: Z, Vhat, W_down0, dO (Z with the
+variance of silu(a) b for independent standard normals a and b, about 0.356;
+the target and the upstream gradient standard normal; W_down0 as above).
 Draw order, LaCT layer: q, k, v, W1, W3, W2.
 """
 from __future__ import annotations
@@ -27,7 +30,7 @@ import torch
 
 __all__ = [
     "InplaceConfig", "LactConfig", "WORKLOADS", "workload",
-    "inplace_inputs", "lact_inputs", "to_f64", "bf16_round",
+    "inplace_inputs", "backward_inputs", "lact_inputs", "to_f64", "bf16_round",
 ]
 
 
@@ -56,6 +59,10 @@ class InplaceConfig:
     docs: int = 1        # documents packed into each row, of equal length in chunks
     conv_forward: bool = False   # forward-looking in-chunk convolution for the target
     pieces: int = 1      # the sequence processed in this many calls, each resuming the previous one
+    backward: bool = False   # the workload is the backward of the dot chunk loop (inputs Z, Vhat, W_down0, dO)
+    var_z: float = 0.356     # backward inputs: Z, the gated intermediate
+    var_vhat: float = 1.0    # backward inputs: the target
+    var_dout: float = 1.0    # backward inputs: the upstream gradient dLoss/dO
 
     @property
     def tokens(self) -> int:
@@ -79,8 +86,12 @@ class InplaceConfig:
 
     def flops(self) -> float:
         """Algorithmic flops of one layer call: producer 4df, target 2d^2 + 2Kd,
-        update 2df, apply 2df per token."""
+        update 2df, apply 2df per token.  Backward of the chunk loop: 10df per
+        token (the states' scan, the suffixes' scan, dVhat, and dZ's two
+        contractions, 2df each)."""
         d, f, K = self.d_model, self.d_ff, self.conv_k
+        if self.backward:
+            return float(self.tokens) * 10.0 * d * f
         return float(self.tokens) * (8.0 * d * f + 2.0 * d * d + 2.0 * K * d)
 
     def with_(self, **kw) -> "InplaceConfig":
@@ -157,6 +168,9 @@ WORKLOADS = {
     # the 128K row packing 8 documents of 16K tokens (4 chunks each)
     "inplace_bf16_128k_8docs": InplaceConfig("inplace_bf16_128k_8docs", 1, 131072, 2560, 9728, 4096, 0.01, "dot", "bf16",
                                              seed=1002, docs=8),
+    # the backward of the 128K layer's dot chunk loop (gradients of Z, V^ and W_down0 from dLoss/dO)
+    "inplace_bwd_bf16_128k": InplaceConfig("inplace_bwd_bf16_128k", 1, 131072, 2560, 9728, 4096, 0.01, "dot", "bf16",
+                                           seed=1005, backward=True),
     "mse_bf16_4x64k": InplaceConfig("mse_bf16_4x64k", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16", seed=1003),
     "lact_bf16_256k": LactConfig("lact_bf16_256k", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004),
     # the LaCT review's own update: dot-product loss, per-token learning rates, L2 weight normalisation
@@ -208,6 +222,22 @@ def inplace_inputs(cfg: InplaceConfig, seed: int | None = None) -> dict:
     out["W_down0"] = _draw(gen, (d, f), cfg.var_down if cfg.var_down is not None else 1.0 / f, dt)
     out["W_target"] = _draw(gen, (d, d), cfg.var_target if cfg.var_target is not None else 1.0 / d, dt)
     out["conv_w"] = _draw(gen, (d, K), cfg.var_conv, dt)
+    return out
+
+
+def backward_inputs(cfg: InplaceConfig, seed: int | None = None) -> dict:
+    """Draw the inputs of the chunk loop's backward on the CPU: Z [B, n, f],
+    Vhat [B, n, d], W_down0 [d, f], dO [B, n, d] (CPU torch tensors in the
+    workload's dtype)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(cfg.seed if seed is None else seed)
+    dt = _torch_dtype(cfg.dtype)
+    B, n, d, f = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff
+    out = {}
+    out["Z"] = _draw(gen, (B, n, f), cfg.var_z, dt)
+    out["Vhat"] = _draw(gen, (B, n, d), cfg.var_vhat, dt)
+    out["W_down0"] = _draw(gen, (d, f), cfg.var_down if cfg.var_down is not None else 1.0 / f, dt)
+    out["dO"] = _draw(gen, (B, n, d), cfg.var_dout, dt)
     return out
 
 
