@@ -217,11 +217,13 @@ int core(const Plan& p, int mode, float eta, const void* Z, const void* V, const
 
 // ------------------------------------------------------------------ backward of the dot chunk loop
 
-// Workspace of ttt_core_backward: the token-contiguous operands of the two
-// scans (Z and eta V^ in order, Z and dO with the chunk order reversed), the
-// forward states W_c and reversed suffix states S, the per-row totals, a zero
-// [d, f] start state, and the scans' own scratch (segment partials, or the
-// per-chunk deltas when the chunk length does not suit the fused scan).
+// Workspace of ttt_core_backward: the recomputed states W_c and the suffix
+// states S (in reverse chunk order), the rows' totals, a zero [d, f] start
+// state, and the scans' operands and scratch.  The fused scan reads Z, V^ and
+// dO in their own layout (only eta V^ is a copy) and keeps segment partials;
+// with a chunk length that does not suit it, the per-chunk deltas read
+// token-contiguous copies (Z and V^ in order, Z and dO in reverse chunk order)
+// and are kept in fp32.
 struct BwdPlan {
   int64_t B, n, d, f, C, k;
   size_t esz;
@@ -250,10 +252,12 @@ int make_bwd_plan(const ttt_inplace_shape* s, int dtype, BwdPlan* p) {
     *o = off;
     off += align_up(bytes);
   };
-  take(&p->off_Zt, BN * p->f * p->esz);
   take(&p->off_Vt, BN * p->d * p->esz);
-  take(&p->off_Zr, BN * p->f * p->esz);
-  take(&p->off_Gr, BN * p->d * p->esz);
+  if (!p->fused) {
+    take(&p->off_Zt, BN * p->f * p->esz);
+    take(&p->off_Zr, BN * p->f * p->esz);
+    take(&p->off_Gr, BN * p->d * p->esz);
+  }
   take(&p->off_Wc, BK * DF * p->esz);
   take(&p->off_Sr, BK * DF * p->esz);
   take(&p->off_T, (size_t)p->B * DF * 4);
@@ -268,16 +272,18 @@ int make_bwd_plan(const ttt_inplace_shape* s, int dtype, BwdPlan* p) {
   return TTT_OK;
 }
 
-// One exclusive scan over the chunks of (Zt, Vt) from W0 into the states Wc and
-// the total Wf: the fused update-scan (Vt already scaled by eta), or deltas and
-// a scan with eta.
+// One exclusive scan over the chunks from W0 into the states Wc and the total
+// Wf: the fused update-scan on row-major Z [B, n, f] and V [B, n, d] (V scaled
+// by eta already), in chunk order or reversed; or deltas of the
+// token-contiguous copies (in the order wanted) and a scan with eta.
 template <typename T>
-int bwd_scan(const BwdPlan& p, const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, float eta, char* ws,
-             hipStream_t s) {
+int bwd_scan(const BwdPlan& p, const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, float eta, bool rev,
+             char* ws, hipStream_t s) {
   const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
   if (p.fused)
     return dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (T*)(ws + p.off_Wp), (float*)(ws + p.off_Tot), B,
-                                                n, d, f, C, p.S, nullptr, nullptr, s));
+                                                n, d, f, C, p.S, nullptr, nullptr, s,
+                                                rev ? ttt::kScanRowMajorReversed : ttt::kScanRowMajor));
   float* dW = (float*)(ws + p.off_dW);
   int st = dev(ttt::launch_chunk_delta<T>(Zt, Vt, dW, B, n, d, f, C, s));
   if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, (int64_t)d * f, eta, nullptr, nullptr, s));
@@ -296,26 +302,34 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
   const T* Z = (const T*)Zv;
   const T* V = (const T*)Vv;
   const T* dO = (const T*)dOv;
-  T* Zt = (T*)(ws + p.off_Zt);
   T* Vt = (T*)(ws + p.off_Vt);
-  T* Zr = (T*)(ws + p.off_Zr);
-  T* Gr = (T*)(ws + p.off_Gr);
   T* Wc = (T*)(ws + p.off_Wc);
   T* Sr = (T*)(ws + p.off_Sr);
   T* Z0 = (T*)(ws + p.off_zero);
   float* Tt = (float*)(ws + p.off_T);
   const T* Slast = Sr + (int64_t)(k - 1) * df;      // S_c = Sr[k - 1 - c]: stride -df from here
-  int st = dev(ttt::launch_transpose<T>(Z, Zt, B, n, f, 1.0f, 0, s));
-  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(V, Vt, B, n, d, p.fused ? eta : 1.0f, 0, s));
-  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zr, B, n, f, 1.0f, C, s));
-  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(dO, Gr, B, n, d, 1.0f, C, s));
-  if (st == TTT_OK) st = dev(ttt::launch_zero<T>(Z0, df, s));
-  // W_c (its W_final lands in Tt and is overwritten by the second scan)
-  if (st == TTT_OK) st = bwd_scan<T>(p, Zt, Vt, (const T*)W0, Wc, Tt, eta, ws, s);
-  // reversed order: Sr[t] = sum of dO_c^T Z_c over the chunks c > k - 1 - t; Tt = all chunks
-  if (st == TTT_OK) st = bwd_scan<T>(p, Zr, Gr, Z0, Sr, Tt, 1.0f, ws, s);
-  if (st == TTT_OK)
-    st = dev(ttt::launch_apply<T>(Zt, Slast, (int64_t)k * df, -df, (T*)dV, B, n, d, f, C, eta, s));
+  int st = dev(ttt::launch_zero<T>(Z0, df, s));
+  if (p.fused) {
+    if (st == TTT_OK) st = dev(ttt::launch_scale<T>(V, Vt, (int64_t)B * n * d, eta, s));
+    // W_c (its W_final lands in Tt and is overwritten by the second scan)
+    if (st == TTT_OK) st = bwd_scan<T>(p, Z, Vt, (const T*)W0, Wc, Tt, eta, false, ws, s);
+    // last chunk first: Sr[t] = sum of dO_c^T Z_c over the chunks c > k - 1 - t; Tt = all chunks
+    if (st == TTT_OK) st = bwd_scan<T>(p, Z, dO, Z0, Sr, Tt, 1.0f, true, ws, s);
+    if (st == TTT_OK)
+      st = dev(ttt::launch_apply<T>(Z, Slast, (int64_t)k * df, -df, (T*)dV, B, n, d, f, C, eta, s, true));
+  } else {
+    T* Zt = (T*)(ws + p.off_Zt);
+    T* Zr = (T*)(ws + p.off_Zr);
+    T* Gr = (T*)(ws + p.off_Gr);
+    if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zt, B, n, f, 1.0f, 0, s));
+    if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(V, Vt, B, n, d, 1.0f, 0, s));
+    if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zr, B, n, f, 1.0f, C, s));
+    if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(dO, Gr, B, n, d, 1.0f, C, s));
+    if (st == TTT_OK) st = bwd_scan<T>(p, Zt, Vt, (const T*)W0, Wc, Tt, eta, false, ws, s);
+    if (st == TTT_OK) st = bwd_scan<T>(p, Zr, Gr, Z0, Sr, Tt, 1.0f, true, ws, s);
+    if (st == TTT_OK)
+      st = dev(ttt::launch_apply<T>(Zt, Slast, (int64_t)k * df, -df, (T*)dV, B, n, d, f, C, eta, s));
+  }
   if (st == TTT_OK)
     st = dev(ttt::launch_dz<T>(dO, V, Wc, (int64_t)k * df, df, Slast, (int64_t)k * df, -df, (T*)dZ, B, n, d, f, C,
                                eta, s));

@@ -7,6 +7,8 @@
 //   Zt [B, f, n]   read by the updates (K = tokens contiguous)
 //   Vt [B, d, n]   the target V^, transposed, read by the updates
 // so that every contraction reads both operands K-contiguously.
+#include <type_traits>
+
 #include "gemm.hpp"
 #include "launch.hpp"
 
@@ -433,7 +435,24 @@ struct SnapshotHook {
   }
 };
 
-template <typename T>
+// An operand whose K steps are taken chunk by chunk in reverse order (the steps
+// inside a chunk keep theirs): step ks of the stream reads the operand's step
+// (last - t) spc + ks - t spc, t = ks / spc, for chunks of spc steps.
+template <class OP>
+struct RevChunks : OP {
+  int spc, last;
+  __device__ __forceinline__ void issue(int ks, char* tile) const {
+    const int t = ks / spc;
+    OP::issue((last - t) * spc + (ks - t * spc), tile);
+  }
+};
+
+// NAT: Zt and Vt are Z [B, n, f] and V [B, n, d] in their row-major layout
+// (tokens are rows), read as MN-major operands; otherwise the token-contiguous
+// copies [B, f, n] and [B, d, n].  REV (with NAT): the chunks are scanned in
+// reverse order, last chunk first; state index c then names the c-th chunk of
+// that order.
+template <typename T, bool NAT, bool REV>
 TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T* __restrict__ Vt,
                                                const T* __restrict__ W0, T* __restrict__ Wc, T* __restrict__ Wp,
                                                float* __restrict__ Tot, float* __restrict__ Wf, int n, int d, int f,
@@ -455,13 +474,28 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
   const int c0 = sg * kS;
   const int j0 = tp * G::BP, i0 = tq * G::BQ;
   const int64_t df = (int64_t)d * f;
-  const uint64_t ldb = (uint64_t)n * esz<T>();
   const unsigned kbytes = (unsigned)kS * C_ * esz<T>();
 
-  DmaOp<G::NW, G::BP> op;
-  DmaOp<G::NW, G::BQ> oq;
-  op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c0 * C_, nullptr, min(G::BP, f - j0), ldb, kbytes);
-  oq.init(Vt + ((int64_t)b * d + i0) * n + (int64_t)c0 * C_, nullptr, min(G::BQ, d - i0), ldb, kbytes);
+  static_assert(NAT || !REV, "the reversed order reads the row-major operands");
+  using OPP = std::conditional_t<NAT, DmaOpMN<T, G::NW, G::BP>, DmaOp<G::NW, G::BP>>;
+  using OPQ = std::conditional_t<NAT, DmaOpMN<T, G::NW, G::BQ>, DmaOp<G::NW, G::BQ>>;
+  std::conditional_t<REV, RevChunks<OPP>, OPP> op;
+  std::conditional_t<REV, RevChunks<OPQ>, OPQ> oq;
+  if constexpr (NAT) {
+    // this segment's tokens: chunks c0 .. c0 + kS - 1 of the scan order, stored from chunk pc0 on
+    const int pc0 = REV ? k - c0 - kS : c0;
+    const int64_t t0 = (int64_t)b * n + (int64_t)pc0 * C_;
+    op.init(Zt + t0 * f + j0, min(G::BP, f - j0), (uint64_t)f * esz<T>(), kS * C_);
+    oq.init(Vt + t0 * d + i0, min(G::BQ, d - i0), (uint64_t)d * esz<T>(), kS * C_);
+    if constexpr (REV) {
+      op.spc = oq.spc = C_ * esz<T>() / 128;
+      op.last = oq.last = kS - 1;
+    }
+  } else {
+    const uint64_t ldb = (uint64_t)n * esz<T>();
+    op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c0 * C_, nullptr, min(G::BP, f - j0), ldb, kbytes);
+    oq.init(Vt + ((int64_t)b * d + i0) * n + (int64_t)c0 * C_, nullptr, min(G::BQ, d - i0), ldb, kbytes);
+  }
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   T* wc = Wc + (int64_t)b * k * df;
@@ -538,7 +572,8 @@ __global__ __launch_bounds__(256) void k_scan_fixup(T* __restrict__ Wc, const T*
 // chunk's tokens, K = d_ff.  W of (b, c) is W + b * wsb + c * wsc.  Z is read
 // from its token-contiguous copy Zt [B, f, n] (the one the updates contract
 // over) as an MN-major operand, so no row-major copy of Z is needed.
-template <typename T>
+// ZNAT: Zt is Z [B, n, f] in its row-major layout, a K-major operand.
+template <typename T, bool ZNAT>
 TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict__ W, int64_t wsb, int64_t wsc,
                                    T* __restrict__ O, int n, int d, int f, int C_, float oscale) {
   using G = Wide;
@@ -556,10 +591,13 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
   const uint64_t ldb = (uint64_t)f * esz<T>();
 
   DmaOp<G::NW, G::BP> op;
-  DmaOpMN<T, G::NW, G::BQ> oq;
+  std::conditional_t<ZNAT, DmaOp<G::NW, G::BQ>, DmaOpMN<T, G::NW, G::BQ>> oq;
   op.init(W + (int64_t)b * wsb + (int64_t)c * wsc + (int64_t)i0 * f, nullptr, min(G::BP, d - i0), ldb,
           (unsigned)ldb);
-  oq.init(Zt + (int64_t)b * f * n + (int64_t)c * C_ + t0, min(G::BQ, C_ - t0), (uint64_t)n * esz<T>(), f);
+  if constexpr (ZNAT)
+    oq.init(Zt + row0 * f, nullptr, min(G::BQ, C_ - t0), ldb, (unsigned)ldb);
+  else
+    oq.init(Zt + (int64_t)b * f * n + (int64_t)c * C_ + t0, min(G::BQ, C_ - t0), (uint64_t)n * esz<T>(), f);
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
@@ -663,6 +701,16 @@ __global__ __launch_bounds__(256) void k_sum_rows(const float* __restrict__ Tot,
   f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int b = 0; b < B; ++b) s += load4(Tot + (int64_t)b * df + e);
   store4(out + e, s[0], s[1], s[2], s[3]);
+}
+
+// dst = scale * src over n elements, four per thread (n % 4 == 0).
+template <typename T>
+__global__ __launch_bounds__(256) void k_scale(const T* __restrict__ src, T* __restrict__ dst, int64_t n,
+                                               float scale) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  const f32x4 v = load4(src + e);
+  store4(dst + e, scale * v[0], scale * v[1], scale * v[2], scale * v[3]);
 }
 
 // p[0 .. n) = 0, four elements per thread (n % 4 == 0).
@@ -888,11 +936,18 @@ hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int
 template <typename T>
 hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
                                     int B, int n, int d, int f, int Cs, int S, const uint8_t* docs,
-                                    const float* Winit, hipStream_t s) {
+                                    const float* Winit, hipStream_t s, int layout) {
   const int64_t tiles = cdiv(f, kWB) * cdiv(d, kWB) * B * S;
   if (tiles == 0) return hipSuccess;
-  k_chunk_update_scan<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f, Cs, S, docs,
-                                                             Winit);
+  if (layout == kScanRowMajorReversed)
+    k_chunk_update_scan<T, true, true><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f, Cs,
+                                                                           S, docs, Winit);
+  else if (layout == kScanRowMajor)
+    k_chunk_update_scan<T, true, false><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f,
+                                                                            Cs, S, docs, Winit);
+  else
+    k_chunk_update_scan<T, false, false><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f,
+                                                                             Cs, S, docs, Winit);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   const int64_t df = (int64_t)d * f;
@@ -903,10 +958,20 @@ hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc
 
 template <typename T>
 hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int Cs,
-                        float oscale, hipStream_t s) {
+                        float oscale, hipStream_t s, bool znat) {
   const int64_t tiles = cdiv(d, kWB) * cdiv(Cs, kWB) * B * (n / Cs);
   if (tiles == 0) return hipSuccess;
-  k_apply<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, W, wsb, wsc, O, n, d, f, Cs, oscale);
+  if (znat)
+    k_apply<T, true><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, W, wsb, wsc, O, n, d, f, Cs, oscale);
+  else
+    k_apply<T, false><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, W, wsb, wsc, O, n, d, f, Cs, oscale);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_scale<T><<<(unsigned)cdiv(n / 4, 256), 256, 0, s>>>(src, dst, n, scale);
   return hipGetLastError();
 }
 
@@ -977,9 +1042,10 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
                                            const uint8_t*, const float*, hipStream_t);                            \
   template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, T*, float*, int,      \
                                                   int, int, int, int, int, const uint8_t*, const float*,          \
-                                                  hipStream_t);                                                   \
+                                                  hipStream_t, int);                                              \
   template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int, float,   \
-                                      hipStream_t);                                                               \
+                                      hipStream_t, bool);                                                         \
+  template hipError_t launch_scale<T>(const T*, T*, int64_t, float, hipStream_t);                                 \
   template hipError_t launch_dz<T>(const T*, const T*, const T*, int64_t, int64_t, const T*, int64_t, int64_t, T*, \
                                    int, int, int, int, int, float, hipStream_t);                                  \
   template hipError_t launch_zero<T>(T*, int64_t, hipStream_t);                                                   \

@@ -24,10 +24,14 @@ hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n,
 template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
                              const uint8_t* docs, const float* Winit, hipStream_t s);
+// Operand layouts of the fused update-scan: the token-contiguous copies Zt
+// [B, f, n] and Vt [B, d, n]; Z [B, n, f] and V [B, n, d] as they are; the
+// latter with the chunks scanned last to first.
+constexpr int kScanTokenContiguous = 0, kScanRowMajor = 1, kScanRowMajorReversed = 2;
 template <typename T>
 hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
                                     int B, int n, int d, int f, int C, int S, const uint8_t* docs, const float* Winit,
-                                    hipStream_t s);
+                                    hipStream_t s, int layout = kScanTokenContiguous);
 
 // Number of sequence segments the fused update-scan runs side by side (a
 // segment count divides the chunk count), by a two-term cost model: the K loop
@@ -52,9 +56,13 @@ inline int update_scan_segments(int64_t d, int64_t f, int64_t k, int64_t C) {
     if (k % cand == 0 && cost(cand) < cost(S)) S = cand;
   return S;
 }
+// znat: Zt is Z [B, n, f] row-major instead of the token-contiguous copy.
 template <typename T>
 hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
-                        float oscale, hipStream_t s);
+                        float oscale, hipStream_t s, bool znat = false);
+// dst [n] = scale * src (n % 4 == 0).
+template <typename T>
+hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_t s);
 // dZ_c = dO_c W_c + eta V_c S_c per chunk (backward of the dot chunk loop);
 // states W_c at W + b wsb + c wsc and S_c at S + b ssb + c ssc, [d, f] each.
 template <typename T>

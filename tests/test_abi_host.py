@@ -194,9 +194,10 @@ def test_step_entry_points_validate():
 
 
 def test_backward_workspace_and_validation():
-    """ttt_core_backward's workspace: Z and eta V^ token-contiguous, the same two with the chunk order reversed,
-    the recomputed states and the suffix states (dtype), the rows' fp32 totals, a zero start state, and the
-    scans' own scratch (segment partials for the fused scan, fp32 deltas otherwise)."""
+    """ttt_core_backward's workspace: eta V^, the recomputed states and the suffix states (dtype), the rows' fp32
+    totals, a zero start state, and the scans' own scratch: segment partials for the fused scan (which reads Z, V^
+    and dO as they are); token-contiguous copies of Z and dO in reverse chunk order, of Z in order, and fp32
+    per-chunk deltas for the delta + scan path."""
     lib = cw.lib()
     al = lambda x: (x + 255) // 256 * 256
     out = ctypes.c_size_t(0)
@@ -208,7 +209,7 @@ def test_backward_workspace_and_validation():
 
     B, n, d, f, C = 2, 2048, 256, 512, 256      # fused, four segments (as the forward plan of this shape)
     k, e = n // C, 2
-    base = 2 * (al(B * n * f * e) + al(B * n * d * e)) + 2 * al(B * k * d * f * e) + al(B * d * f * 4) + al(d * f * e)
+    base = al(B * n * d * e) + 2 * al(B * k * d * f * e) + al(B * d * f * 4) + al(d * f * e)
     assert ws(B, n, d, f, C) == (cw.TTT_OK, base + al(B * (k - k // 4) * d * f * e) + al(B * 3 * d * f * 4))
     # chunk 40: not on the 64-token step of the fused scan, so per-chunk fp32 deltas
     n2, C2 = 2000, 40
