@@ -219,17 +219,17 @@ int core(const Plan& p, int mode, float eta, const void* Z, const void* V, const
 
 // Workspace of ttt_core_backward: the recomputed states W_c and the suffix
 // states S (in reverse chunk order), the rows' totals, a zero [d, f] start
-// state, and the scans' operands and scratch.  The fused scan reads Z, V^ and
-// dO in their own layout (only eta V^ is a copy) and keeps segment partials;
-// with a chunk length that does not suit it, the per-chunk deltas read
-// token-contiguous copies (Z and V^ in order, Z and dO in reverse chunk order)
-// and are kept in fp32.
+// state, eta V^ (row-major, for dZ), and the scans' operands and scratch.  The
+// fused scan reads Z, eta V^ and dO in their own layout and keeps segment
+// partials; with a chunk length that does not suit it, the per-chunk deltas
+// read token-contiguous copies (Z and V^ in order, Z and dO in reverse chunk
+// order) and are kept in fp32.
 struct BwdPlan {
   int64_t B, n, d, f, C, k;
   size_t esz;
   bool fused;
   int S;
-  size_t off_Zt, off_Vt, off_Zr, off_Gr, off_Wc, off_Sr, off_T, off_zero, off_Wp, off_Tot, off_dW, total;
+  size_t off_Zt, off_Vt, off_Vs, off_Zr, off_Gr, off_Wc, off_Sr, off_T, off_zero, off_Wp, off_Tot, off_dW, total;
 };
 
 int make_bwd_plan(const ttt_inplace_shape* s, int dtype, BwdPlan* p) {
@@ -252,8 +252,9 @@ int make_bwd_plan(const ttt_inplace_shape* s, int dtype, BwdPlan* p) {
     *o = off;
     off += align_up(bytes);
   };
-  take(&p->off_Vt, BN * p->d * p->esz);
+  take(&p->off_Vs, BN * p->d * p->esz);
   if (!p->fused) {
+    take(&p->off_Vt, BN * p->d * p->esz);
     take(&p->off_Zt, BN * p->f * p->esz);
     take(&p->off_Zr, BN * p->f * p->esz);
     take(&p->off_Gr, BN * p->d * p->esz);
@@ -302,23 +303,24 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
   const T* Z = (const T*)Zv;
   const T* V = (const T*)Vv;
   const T* dO = (const T*)dOv;
-  T* Vt = (T*)(ws + p.off_Vt);
+  T* Vs = (T*)(ws + p.off_Vs);     // eta V^ [B, n, d]
   T* Wc = (T*)(ws + p.off_Wc);
   T* Sr = (T*)(ws + p.off_Sr);
   T* Z0 = (T*)(ws + p.off_zero);
   float* Tt = (float*)(ws + p.off_T);
   const T* Slast = Sr + (int64_t)(k - 1) * df;      // S_c = Sr[k - 1 - c]: stride -df from here
   int st = dev(ttt::launch_zero<T>(Z0, df, s));
+  if (st == TTT_OK) st = dev(ttt::launch_scale<T>(V, Vs, (int64_t)B * n * d, eta, s));
   if (p.fused) {
-    if (st == TTT_OK) st = dev(ttt::launch_scale<T>(V, Vt, (int64_t)B * n * d, eta, s));
     // W_c (its W_final lands in Tt and is overwritten by the second scan)
-    if (st == TTT_OK) st = bwd_scan<T>(p, Z, Vt, (const T*)W0, Wc, Tt, eta, false, ws, s);
+    if (st == TTT_OK) st = bwd_scan<T>(p, Z, Vs, (const T*)W0, Wc, Tt, eta, false, ws, s);
     // last chunk first: Sr[t] = sum of dO_c^T Z_c over the chunks c > k - 1 - t; Tt = all chunks
     if (st == TTT_OK) st = bwd_scan<T>(p, Z, dO, Z0, Sr, Tt, 1.0f, true, ws, s);
     if (st == TTT_OK)
       st = dev(ttt::launch_apply<T>(Z, Slast, (int64_t)k * df, -df, (T*)dV, B, n, d, f, C, eta, s, true));
   } else {
     T* Zt = (T*)(ws + p.off_Zt);
+    T* Vt = (T*)(ws + p.off_Vt);
     T* Zr = (T*)(ws + p.off_Zr);
     T* Gr = (T*)(ws + p.off_Gr);
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zt, B, n, f, 1.0f, 0, s));
@@ -331,8 +333,8 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
       st = dev(ttt::launch_apply<T>(Zt, Slast, (int64_t)k * df, -df, (T*)dV, B, n, d, f, C, eta, s));
   }
   if (st == TTT_OK)
-    st = dev(ttt::launch_dz<T>(dO, V, Wc, (int64_t)k * df, df, Slast, (int64_t)k * df, -df, (T*)dZ, B, n, d, f, C,
-                               eta, s));
+    st = dev(ttt::launch_dz<T>(dO, Vs, Wc, (int64_t)k * df, df, Slast, (int64_t)k * df, -df, (T*)dZ, B, n, d, f, C,
+                               s));
   if (st == TTT_OK) st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
   return st;
 }

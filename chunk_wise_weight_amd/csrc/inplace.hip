@@ -627,17 +627,34 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
 
 // ------------------------------------------------------------------ backward of the dot chunk loop
 
+// Two operands of one tile shape read back to back along K: steps 0 .. n1 - 1
+// from the first, the rest from the second.  They share the LDS layout, so one
+// accumulator takes the sum of both contractions in one stream of K steps.
+template <class OP>
+struct Concat {
+  OP a, b;
+  int n1;
+  static constexpr int kReads = OP::kReads;
+  __device__ static __forceinline__ u32x4 frag(const char* t, int m0, int g) { return OP::frag(t, m0, g); }
+  __device__ __forceinline__ void issue(int ks, char* tile) const {
+    if (ks < n1)
+      a.issue(ks, tile);
+    else
+      b.issue(ks - n1, tile);
+  }
+};
+
 // dZ_j = dO_j W_j + eta V^_j S_j for every chunk j, with W_j the state chunk j
 // was applied with and S_j = sum_{c>j} dO_c^T Z_c (Method §3's prefix form
 // differentiated; see the backward entry point).  P = d_ff columns of the
-// [d, f] states (MN-major: f contiguous), Q = the chunk's tokens (rows of V^ and
-// dO, [n, d]), K = d_model: one K loop over (S_j, V^_j), the accumulator scaled
-// by eta, a second over (W_j, dO_j).  State j sits at W + b wsb + j wsc (S
+// [d, f] states (MN-major: f contiguous), Q = the chunk's tokens (rows of
+// eta V^ and dO, [n, d]), K = d_model twice: one stream of K steps over
+// (S_j, eta V^_j), then (W_j, dO_j).  State j sits at W + b wsb + j wsc (S
 // likewise; its stride may be negative).  dZ [B, n, f] through LDS like O.
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ V, const T* __restrict__ W,
                                 int64_t wsb, int64_t wsc, const T* __restrict__ S, int64_t ssb, int64_t ssc,
-                                T* __restrict__ dZ, int n, int d, int f, int C_, float eta) {
+                                T* __restrict__ dZ, int n, int d, int f, int C_) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (f + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
@@ -655,24 +672,15 @@ TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ 
   const int nks = (d + KR - 1) / KR;
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
-  {
-    DmaOpMN<T, G::NW, G::BP> op;
-    DmaOp<G::NW, G::BQ> oq;
-    op.init(S + (int64_t)b * ssb + (int64_t)c * ssc + j0, min(G::BP, f - j0), ldf, d);
-    oq.init(V + row0 * d, nullptr, min(G::BQ, C_ - t0), ldd, (unsigned)ldd);
-    mainloop<T, G>(op, oq, nks, acc, smem, NoHook{});
-  }
-#pragma unroll
-  for (int i = 0; i < G::NPB; ++i)
-#pragma unroll
-    for (int j = 0; j < G::NQB; ++j) acc[i][j] *= eta;
-  {
-    DmaOpMN<T, G::NW, G::BP> op;
-    DmaOp<G::NW, G::BQ> oq;
-    op.init(W + (int64_t)b * wsb + (int64_t)c * wsc + j0, min(G::BP, f - j0), ldf, d);
-    oq.init(dO + row0 * d, nullptr, min(G::BQ, C_ - t0), ldd, (unsigned)ldd);
-    mainloop<T, G>(op, oq, nks, acc, smem, NoHook{});
-  }
+  Concat<DmaOpMN<T, G::NW, G::BP>> op;
+  Concat<DmaOp<G::NW, G::BQ>> oq;
+  op.a.init(S + (int64_t)b * ssb + (int64_t)c * ssc + j0, min(G::BP, f - j0), ldf, d);
+  op.b.init(W + (int64_t)b * wsb + (int64_t)c * wsc + j0, min(G::BP, f - j0), ldf, d);
+  oq.a.init(V + row0 * d, nullptr, min(G::BQ, C_ - t0), ldd, (unsigned)ldd);
+  oq.b.init(dO + row0 * d, nullptr, min(G::BQ, C_ - t0), ldd, (unsigned)ldd);
+  op.n1 = oq.n1 = nks;
+  mainloop<T, G>(op, oq, 2 * nks, acc, smem, NoHook{});
+
   const int tn = min(G::BQ, C_ - t0), jn = min(G::BP, f - j0);
   constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
   const Staged<T, G::BP> st{smem};
@@ -977,10 +985,10 @@ hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_
 
 template <typename T>
 hipError_t launch_dz(const T* dO, const T* V, const T* W, int64_t wsb, int64_t wsc, const T* S, int64_t ssb,
-                     int64_t ssc, T* dZ, int B, int n, int d, int f, int Cs, float eta, hipStream_t s) {
+                     int64_t ssc, T* dZ, int B, int n, int d, int f, int Cs, hipStream_t s) {
   const int64_t tiles = cdiv(f, kWB) * cdiv(Cs, kWB) * B * (n / Cs);
   if (tiles == 0) return hipSuccess;
-  k_dz<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(dO, V, W, wsb, wsc, S, ssb, ssc, dZ, n, d, f, Cs, eta);
+  k_dz<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(dO, V, W, wsb, wsc, S, ssb, ssc, dZ, n, d, f, Cs);
   return hipGetLastError();
 }
 
@@ -1047,7 +1055,7 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
                                       hipStream_t, bool);                                                         \
   template hipError_t launch_scale<T>(const T*, T*, int64_t, float, hipStream_t);                                 \
   template hipError_t launch_dz<T>(const T*, const T*, const T*, int64_t, int64_t, const T*, int64_t, int64_t, T*, \
-                                   int, int, int, int, int, float, hipStream_t);                                  \
+                                   int, int, int, int, int, hipStream_t);                                         \
   template hipError_t launch_zero<T>(T*, int64_t, hipStream_t);                                                   \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
                                           const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t); \

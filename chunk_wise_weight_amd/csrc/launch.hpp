@@ -63,11 +63,11 @@ hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O,
 // dst [n] = scale * src (n % 4 == 0).
 template <typename T>
 hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_t s);
-// dZ_c = dO_c W_c + eta V_c S_c per chunk (backward of the dot chunk loop);
-// states W_c at W + b wsb + c wsc and S_c at S + b ssb + c ssc, [d, f] each.
+// dZ_c = dO_c W_c + V_c S_c per chunk, V = eta V^ (backward of the dot chunk
+// loop); states W_c at W + b wsb + c wsc and S_c at S + b ssb + c ssc, [d, f].
 template <typename T>
 hipError_t launch_dz(const T* dO, const T* V, const T* W, int64_t wsb, int64_t wsc, const T* S, int64_t ssb,
-                     int64_t ssc, T* dZ, int B, int n, int d, int f, int C, float eta, hipStream_t s);
+                     int64_t ssc, T* dZ, int B, int n, int d, int f, int C, hipStream_t s);
 // out [df] = sum over b of Tot [B, df] (fp32; df % 4 == 0).
 hipError_t launch_sum_rows(const float* Tot, float* out, int B, int64_t df, hipStream_t s);
 // p [n] = 0 (n % 4 == 0).

@@ -194,7 +194,7 @@ def test_step_entry_points_validate():
 
 
 def test_backward_workspace_and_validation():
-    """ttt_core_backward's workspace: eta V^, the recomputed states and the suffix states (dtype), the rows' fp32
+    """ttt_core_backward's workspace: eta V^ (row-major), the recomputed states and the suffix states (dtype), the rows' fp32
     totals, a zero start state, and the scans' own scratch: segment partials for the fused scan (which reads Z, V^
     and dO as they are); token-contiguous copies of Z and dO in reverse chunk order, of Z in order, and fp32
     per-chunk deltas for the delta + scan path."""
@@ -214,8 +214,8 @@ def test_backward_workspace_and_validation():
     # chunk 40: not on the 64-token step of the fused scan, so per-chunk fp32 deltas
     n2, C2 = 2000, 40
     k2 = n2 // C2
-    base2 = 2 * (al(B * n2 * f * e) + al(B * n2 * d * e)) + 2 * al(B * k2 * d * f * e) + al(B * d * f * 4) + \
-        al(d * f * e)
+    base2 = al(B * n2 * d * e) + 2 * (al(B * n2 * f * e) + al(B * n2 * d * e)) + 2 * al(B * k2 * d * f * e) + \
+        al(B * d * f * 4) + al(d * f * e)
     assert ws(B, n2, d, f, C2) == (cw.TTT_OK, base2 + al(B * k2 * d * f * 4))
     assert ws(0, n, d, f, C) == (cw.TTT_OK, 0) and ws(B, 0, d, f, C) == (cw.TTT_OK, 0)
     assert ws(B, 2000, d, f, C)[0] == cw.TTT_ERR_SHAPE
