@@ -154,9 +154,17 @@ def bench_generic(cfg, steps, warmup):
         dV = torch.empty(B, n, d, dtype=dt, device="cuda")
         dW0 = torch.empty(d, f, dtype=torch.float32, device="cuda")
         shape = cw.InplaceShape(B, n, d, f, cfg.chunk, 1)
-        ws = torch.empty(max(1, cw.ttt_core_backward_workspace_bytes(shape, dt)), dtype=torch.uint8, device="cuda")
+        Ws = None
+        if cfg.kept_states:
+            # the forward chunk loop keeps its states (before the timed region, like the other inputs)
+            Ws = torch.empty(B, n // cfg.chunk, d, f, dtype=dt, device="cuda")
+            cw.ttt_core_apply_update(g["Z"], g["Vhat"], g["W_down0"], cfg.chunk, cfg.eta, "dot", W_states=Ws)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        nbytes = cw.ttt_core_backward_workspace_bytes(shape, dt, cfg.kept_states)
+        ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
         call = lambda: cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta, dZ, dV,
-                                            dW0, ws)
+                                            dW0, ws, W_states=Ws)
     elif isinstance(cfg, ti.LactConfig):
         x = ti.lact_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
@@ -307,6 +315,7 @@ def main():
             out["config"]["calls_per_sequence"] = cfg.pieces
         if cfg.backward:
             out["config"]["pass"] = "backward of the chunk loop (dZ, dVhat, dW_down0 from dLoss/dO)"
+            out["config"]["states"] = "kept by the forward call" if cfg.kept_states else "recomputed"
             out["metric"] = "TTT chunk-loop backward tokens/s at 128K ctx; % of bf16 MFMA peak"
 
     if (not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot" and cfg.docs == 1 and not cfg.conv_forward and

@@ -28,7 +28,7 @@ class InplaceShape(ctypes.Structure):
 
 class LayerOptions(ctypes.Structure):
     _fields_ = [("doc_starts", ctypes.c_void_p), ("conv_forward", ctypes.c_int), ("W_init", ctypes.c_void_p),
-                ("x0_halo", ctypes.c_void_p)]
+                ("x0_halo", ctypes.c_void_p), ("W_states", ctypes.c_void_p)]
 
 
 class LactOptions(ctypes.Structure):
@@ -58,8 +58,10 @@ _SIGNATURES = {
     "ttt_chunk_apply_update_ex": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.POINTER(LayerOptions), _P, _P, _P, _S, _P]),
     "ttt_core_apply_update": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _S, _P]),
-    "ttt_core_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, ctypes.POINTER(_S)]),
-    "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "ttt_core_apply_update_ex": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P,
+                                      ctypes.POINTER(LayerOptions), _P, _P, _P, _S, _P]),
+    "ttt_core_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
+    "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "ttt_produce_z": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P, _P]),
     "ttt_vhat_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, ctypes.POINTER(_S)]),
     "ttt_produce_vhat": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _S, _P]),
@@ -162,13 +164,14 @@ def _workspace(nbytes: int, device, workspace):
 
 def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk: int, eta: float, mode="dot",
                            O=None, W_final=None, workspace=None, doc_starts=None, conv_forward=False, W_init=None,
-                           x0_halo=None):
+                           x0_halo=None, W_states=None):
     """The whole In-Place layer.  Returns (O [B, n, d], W_final [B, d, f] fp32).
 
     Options (ttt_chunk_apply_update_ex): doc_starts, a uint8 (or bool) device tensor [B, seq_len // chunk] whose
     nonzero entries mark the chunks that start a new document in their row; conv_forward, the forward-looking
     in-chunk convolution for the target; W_init [B, d, f] fp32 and x0_halo [B, K-1, d] to resume rows from an
-    earlier call (its W_final and its last K-1 rows of X0)."""
+    earlier call (its W_final and its last K-1 rows of X0); W_states [B, seq_len // chunk, d, f] (dtype) to keep
+    the per-chunk states of the dot objective for ttt_core_backward."""
     B, n, d = H.shape
     f = W_gate.shape[0]
     K = conv_w.shape[1]
@@ -188,7 +191,9 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
         _need(W_init, "W_init", (B, d, f), torch.float32, dev)
     if x0_halo is not None:
         _need(x0_halo, "x0_halo", (B, K - 1, d), dt, dev)
-    if doc_starts is None and not conv_forward and W_init is None and x0_halo is None:
+    if W_states is not None:
+        _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
+    if doc_starts is None and not conv_forward and W_init is None and x0_halo is None and W_states is None:
         _check(lib().ttt_chunk_apply_update(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
                                             _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
                                             _ptr(conv_w), _ptr(O), _ptr(W_final), _ptr(ws), nbytes, _stream(dev)),
@@ -199,7 +204,7 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
             doc_starts = doc_starts.to(torch.uint8)
         _need(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), torch.uint8, dev)
     ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
-    opts = LayerOptions(ptr(doc_starts), 1 if conv_forward else 0, ptr(W_init), ptr(x0_halo))
+    opts = LayerOptions(ptr(doc_starts), 1 if conv_forward else 0, ptr(W_init), ptr(x0_halo), ptr(W_states))
     _check(lib().ttt_chunk_apply_update_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
                                            _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
                                            _ptr(conv_w), ctypes.byref(opts), _ptr(O), _ptr(W_final), _ptr(ws),
@@ -209,8 +214,9 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
 
 
 def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", O=None, W_final=None,
-                          workspace=None):
-    """The chunk loop given Z [B, n, f] and Vhat [B, n, d].  Returns (O, W_final)."""
+                          workspace=None, W_states=None):
+    """The chunk loop given Z [B, n, f] and Vhat [B, n, d].  Returns (O, W_final).  W_states [B, n // chunk, d, f]
+    (dtype), if given, receives the per-chunk states of the dot objective (ttt_core_apply_update_ex)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
     dt, dev = Z.dtype, Z.device
@@ -224,22 +230,32 @@ def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", 
     _need(W_final, "W_final", (B, d, f), torch.float32, dev)
     nbytes = ttt_inplace_workspace_bytes(shape, dt, mode, False)
     ws = _workspace(nbytes, dev, workspace)
+    if W_states is not None:
+        _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
+        opts = LayerOptions(None, 0, None, None, ctypes.c_void_p(W_states.data_ptr()) if W_states.numel() else None)
+        _check(lib().ttt_core_apply_update_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(Z),
+                                              _ptr(Vhat), _ptr(W_down0), ctypes.byref(opts), _ptr(O), _ptr(W_final),
+                                              _ptr(ws), nbytes, _stream(dev)),
+               "ttt_core_apply_update_ex")
+        return O, W_final
     _check(lib().ttt_core_apply_update(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(Z), _ptr(Vhat),
                                        _ptr(W_down0), _ptr(O), _ptr(W_final), _ptr(ws), nbytes, _stream(dev)),
            "ttt_core_apply_update")
     return O, W_final
 
 
-def ttt_core_backward_workspace_bytes(shape: InplaceShape, dtype: torch.dtype) -> int:
+def ttt_core_backward_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, saved_states=False) -> int:
     n = ctypes.c_size_t()
-    _check(lib().ttt_core_backward_workspace_bytes(ctypes.byref(shape), _dt(dtype), ctypes.byref(n)),
+    _check(lib().ttt_core_backward_workspace_bytes(ctypes.byref(shape), _dt(dtype), int(bool(saved_states)),
+                                                   ctypes.byref(n)),
            "ttt_core_backward_workspace_bytes")
     return n.value
 
 
 def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVhat=None, dW_down0=None,
-                      workspace=None):
-    """Gradients through the dot chunk loop given dO = dLoss/dO [B, n, d].
+                      workspace=None, W_states=None):
+    """Gradients through the dot chunk loop given dO = dLoss/dO [B, n, d], with the per-chunk states W_states
+    [B, n // chunk, d, f] kept by the forward call, or recomputed (None).
     Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
@@ -255,10 +271,14 @@ def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVh
     _need(dZ, "dZ", (B, n, f), dt, dev)
     _need(dVhat, "dVhat", (B, n, d), dt, dev)
     _need(dW_down0, "dW_down0", (d, f), torch.float32, dev)
-    nbytes = ttt_core_backward_workspace_bytes(shape, dt)
+    if W_states is not None:
+        _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
+    nbytes = ttt_core_backward_workspace_bytes(shape, dt, W_states is not None)
     ws = _workspace(nbytes, dev, workspace)
+    sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
     _check(lib().ttt_core_backward(ctypes.byref(shape), _dt(dt), float(eta), _ptr(Z), _ptr(Vhat), _ptr(W_down0),
-                                   _ptr(dO), _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes, _stream(dev)),
+                                   _ptr(dO), sp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
+                                   _stream(dev)),
            "ttt_core_backward")
     return dZ, dVhat, dW_down0
 

@@ -31,6 +31,7 @@ struct Plan {
   bool conv_fwd;        // forward-looking in-chunk convolution for the target
   const float* Winit;   // resumed rows: state before chunk 0 [B, d, f] fp32 (device) or null
   const void* halo;     // resumed rows: X0 rows before the first token [B, K-1, d] (device) or null
+  void* states;         // dot objective: where the per-chunk states go [B, k, d, f] (device), or null: workspace
 };
 
 int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
@@ -60,6 +61,7 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   p->conv_fwd = false;
   p->Winit = nullptr;
   p->halo = nullptr;
+  p->states = nullptr;
   p->B = s->batch;
   p->n = s->seq_len;
   p->d = s->d_model;
@@ -153,7 +155,7 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
     }
     return TTT_OK;
   }
-  T* Wc = (T*)(ws + p.off_Wc);
+  T* Wc = p.states != nullptr ? (T*)p.states : (T*)(ws + p.off_Wc);
   int st;
   if (p.fused) {
     st = dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (T*)(ws + p.off_Wp), (float*)(ws + p.off_Tot),
@@ -182,6 +184,25 @@ int run_producers(const Plan& p, const void* H, const void* X0, const void* Wg, 
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Wt, WtT, 1, d, d, 1.0f, 0, s));
   if (st == TTT_OK) st = dev(ttt::launch_produce_vhat<T>(Y, WtT, Vt, rows, n, d, vscale, s));
   return st;
+}
+
+// Options common to the layer and the chunk loop; `producers`: the target
+// producer's options (conv_forward, x0_halo) apply.
+int apply_options(Plan& p, int mode, const ttt_layer_options* o, bool producers) {
+  if (o == nullptr) return TTT_OK;
+  if (producers && o->conv_forward != 0 && o->conv_forward != 1) return TTT_ERR_ARG;
+  if ((o->W_init != nullptr && !ok_ptr(o->W_init)) || (producers && o->x0_halo != nullptr && !ok_ptr(o->x0_halo)) ||
+      (o->W_states != nullptr && !ok_ptr(o->W_states)))
+    return TTT_ERR_ARG;
+  if (o->W_states != nullptr && mode == TTT_MODE_MSE) return TTT_ERR_ARG;
+  p.docs = o->doc_starts;
+  p.Winit = o->W_init;
+  p.states = o->W_states;
+  if (producers) {
+    p.conv_fwd = o->conv_forward == 1;
+    p.halo = p.K > 1 ? o->x0_halo : nullptr;
+  }
+  return TTT_OK;
 }
 
 int check_ws(const Plan& p, void* ws, size_t bytes) {
@@ -228,14 +249,16 @@ struct BwdPlan {
   int64_t B, n, d, f, C, k;
   size_t esz;
   bool fused;
+  bool saved;         // the states come from the caller
   int S;
   size_t off_Zt, off_Vt, off_Vs, off_Zr, off_Gr, off_Wc, off_Sr, off_T, off_zero, off_Wp, off_Tot, off_dW, total;
 };
 
-int make_bwd_plan(const ttt_inplace_shape* s, int dtype, BwdPlan* p) {
+int make_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, BwdPlan* p) {
   int st = check_inplace_shape(s, dtype);
   if (st != TTT_OK) return st;
   memset(p, 0, sizeof(*p));
+  p->saved = saved;
   p->B = s->batch;
   p->n = s->seq_len;
   p->d = s->d_model;
@@ -259,7 +282,7 @@ int make_bwd_plan(const ttt_inplace_shape* s, int dtype, BwdPlan* p) {
     take(&p->off_Zr, BN * p->f * p->esz);
     take(&p->off_Gr, BN * p->d * p->esz);
   }
-  take(&p->off_Wc, BK * DF * p->esz);
+  if (!saved) take(&p->off_Wc, BK * DF * p->esz);
   take(&p->off_Sr, BK * DF * p->esz);
   take(&p->off_T, (size_t)p->B * DF * 4);
   take(&p->off_zero, DF * p->esz);
@@ -296,7 +319,7 @@ int bwd_scan(const BwdPlan& p, const T* Zt, const T* Vt, const T* W0, T* Wc, flo
 // sequences, and dW_down0 as the sum of the rows' totals.
 template <typename T>
 int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, const void* W0, const void* dOv,
-                  void* dZ, void* dV, float* dW0, char* ws, hipStream_t s) {
+                  const void* Wsaved, void* dZ, void* dV, float* dW0, char* ws, hipStream_t s) {
   const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
   const int64_t df = (int64_t)d * f;
   if (p.B * p.n == 0) return dev(ttt::launch_zero<float>(dW0, df, s));
@@ -304,7 +327,7 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
   const T* V = (const T*)Vv;
   const T* dO = (const T*)dOv;
   T* Vs = (T*)(ws + p.off_Vs);     // eta V^ [B, n, d]
-  T* Wc = (T*)(ws + p.off_Wc);
+  T* Wc = p.saved ? (T*)Wsaved : (T*)(ws + p.off_Wc);
   T* Sr = (T*)(ws + p.off_Sr);
   T* Z0 = (T*)(ws + p.off_zero);
   float* Tt = (float*)(ws + p.off_T);
@@ -313,7 +336,7 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
   if (st == TTT_OK) st = dev(ttt::launch_scale<T>(V, Vs, (int64_t)B * n * d, eta, s));
   if (p.fused) {
     // W_c (its W_final lands in Tt and is overwritten by the second scan)
-    if (st == TTT_OK) st = bwd_scan<T>(p, Z, Vs, (const T*)W0, Wc, Tt, eta, false, ws, s);
+    if (st == TTT_OK && !p.saved) st = bwd_scan<T>(p, Z, Vs, (const T*)W0, Wc, Tt, eta, false, ws, s);
     // last chunk first: Sr[t] = sum of dO_c^T Z_c over the chunks c > k - 1 - t; Tt = all chunks
     if (st == TTT_OK) st = bwd_scan<T>(p, Z, dO, Z0, Sr, Tt, 1.0f, true, ws, s);
     if (st == TTT_OK)
@@ -324,10 +347,10 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
     T* Zr = (T*)(ws + p.off_Zr);
     T* Gr = (T*)(ws + p.off_Gr);
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zt, B, n, f, 1.0f, 0, s));
-    if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(V, Vt, B, n, d, 1.0f, 0, s));
+    if (st == TTT_OK && !p.saved) st = dev(ttt::launch_transpose<T>(V, Vt, B, n, d, 1.0f, 0, s));
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zr, B, n, f, 1.0f, C, s));
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(dO, Gr, B, n, d, 1.0f, C, s));
-    if (st == TTT_OK) st = bwd_scan<T>(p, Zt, Vt, (const T*)W0, Wc, Tt, eta, false, ws, s);
+    if (st == TTT_OK && !p.saved) st = bwd_scan<T>(p, Zt, Vt, (const T*)W0, Wc, Tt, eta, false, ws, s);
     if (st == TTT_OK) st = bwd_scan<T>(p, Zr, Gr, Z0, Sr, Tt, 1.0f, true, ws, s);
     if (st == TTT_OK)
       st = dev(ttt::launch_apply<T>(Zt, Slast, (int64_t)k * df, -df, (T*)dV, B, n, d, f, C, eta, s));
@@ -403,16 +426,7 @@ int ttt_chunk_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mod
       return TTT_ERR_ARG;
   }
   if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
-  if (options != nullptr) {
-    if (options->conv_forward != 0 && options->conv_forward != 1) return TTT_ERR_ARG;
-    if ((options->W_init != nullptr && !ok_ptr(options->W_init)) ||
-        (options->x0_halo != nullptr && !ok_ptr(options->x0_halo)))
-      return TTT_ERR_ARG;
-    p.docs = options->doc_starts;
-    p.conv_fwd = options->conv_forward == 1;
-    p.Winit = options->W_init;
-    p.halo = p.K > 1 ? options->x0_halo : nullptr;
-  }
+  if ((st = apply_options(p, mode, options, true)) != TTT_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if (dtype == TTT_BF16)
@@ -423,6 +437,13 @@ int ttt_chunk_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mod
 int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* Z,
                           const void* Vhat, const void* W_down0, void* O, float* W_final, void* workspace,
                           size_t workspace_bytes, void* stream) {
+  return ttt_core_apply_update_ex(shape, dtype, mode, eta, Z, Vhat, W_down0, nullptr, O, W_final, workspace,
+                                  workspace_bytes, stream);
+}
+
+int ttt_core_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* Z,
+                             const void* Vhat, const void* W_down0, const ttt_layer_options* options, void* O,
+                             float* W_final, void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
   int st = make_plan(shape, dtype, mode, false, &p);
   if (st != TTT_OK) return st;
@@ -432,28 +453,29 @@ int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, f
     if (p.n > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(O))) return TTT_ERR_ARG;
   }
   if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
+  if ((st = apply_options(p, mode, options, false)) != TTT_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == TTT_BF16) return core<bf16>(p, mode, eta, Z, Vhat, W_down0, O, W_final, (char*)workspace, s);
   return core<float>(p, mode, eta, Z, Vhat, W_down0, O, W_final, (char*)workspace, s);
 }
 
-int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes) {
+int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states, size_t* bytes) {
   if (bytes == nullptr) return TTT_ERR_ARG;
   BwdPlan p;
-  int st = make_bwd_plan(shape, dtype, &p);
+  int st = make_bwd_plan(shape, dtype, saved_states != 0, &p);
   if (st != TTT_OK) return st;
   *bytes = p.total;
   return TTT_OK;
 }
 
 int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
-                      const void* W_down0, const void* dO, void* dZ, void* dVhat, float* dW_down0, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      const void* W_down0, const void* dO, const void* W_states, void* dZ, void* dVhat,
+                      float* dW_down0, void* workspace, size_t workspace_bytes, void* stream) {
   BwdPlan p;
-  int st = make_bwd_plan(shape, dtype, &p);
+  int st = make_bwd_plan(shape, dtype, W_states != nullptr, &p);
   if (st != TTT_OK) return st;
   if (!finite(eta)) return TTT_ERR_ARG;
-  if (!ok_ptr(dW_down0)) return TTT_ERR_ARG;
+  if (!ok_ptr(dW_down0) || (W_states != nullptr && !aligned16(W_states))) return TTT_ERR_ARG;
   if (p.B * p.n > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(W_down0) || !ok_ptr(dO) || !ok_ptr(dZ) ||
                         !ok_ptr(dVhat)))
     return TTT_ERR_ARG;
@@ -461,8 +483,8 @@ int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, cons
     return TTT_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == TTT_BF16)
-    return core_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, dZ, dVhat, dW_down0, (char*)workspace, s);
-  return core_backward<float>(p, eta, Z, Vhat, W_down0, dO, dZ, dVhat, dW_down0, (char*)workspace, s);
+    return core_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
+  return core_backward<float>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
 }
 
 int ttt_produce_z(const ttt_inplace_shape* shape, int dtype, const void* H, const void* W_gate, const void* W_up,

@@ -160,6 +160,13 @@ typedef struct {
    * results up to rounding order. */
   const float* W_init;
   const void* x0_halo;
+  /* Keeping the states for a backward pass (dot objective: TTT_MODE_DOT or
+   * TTT_MODE_DOT_SCAN): W_states [B, k, d, f] dtype (DEVICE, 16-byte
+   * aligned) receives the state each chunk was applied with, W_states[b, c] =
+   * W_c, in place of the workspace copy the call keeps anyway, so keeping
+   * them costs nothing.  ttt_core_backward takes them to skip recomputing
+   * the states.  NULL: not kept.  With the MSE objective: TTT_ERR_ARG. */
+  void* W_states;
 } ttt_layer_options;
 
 /* The layer of ttt_chunk_apply_update with options (above); same arguments,
@@ -178,12 +185,23 @@ int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, f
                           void* O, float* W_final, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* The chunk loop with options: doc_starts, W_init and W_states as for the
+ * layer (conv_forward and x0_halo concern the target producer and are not
+ * read). */
+int ttt_core_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mode, float eta,
+                             const void* Z, const void* Vhat, const void* W_down0,
+                             const ttt_layer_options* options, void* O, float* W_final,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- backward of the dot chunk loop ---- */
 
-/* Workspace bytes for ttt_core_backward: about 2 B (k d f + 2 n (d + f)) dtype
- * elements plus B d f fp32 (the recomputed states, the suffix states and the
- * transposed operands below). */
-int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes);
+/* Workspace bytes for ttt_core_backward, with the states given (saved_states
+ * = 1) or recomputed (0): about B (2 k d f + n d) dtype elements plus B d f
+ * fp32 (the recomputed states, the suffix states, eta V^), one k d f less
+ * with saved states; with a chunk length the fused scan does not take (see
+ * ttt_chunk_update_scan), token-contiguous copies and fp32 deltas besides. */
+int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states,
+                                      size_t* bytes);
 
 /* Gradients through the dot-objective chunk loop (ttt_core_apply_update with
  * TTT_MODE_DOT), for a loss that depends on O alone, given its gradient
@@ -196,9 +214,11 @@ int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype,
  *   dW_down0 [d, f]    fp32:   sum over rows and chunks of dO_c^T Z_c
  *                              (W_down0 is shared by the rows, so their
  *                              gradients add).
- * The states W_c are recomputed by the chunk scan; the suffixes come from the
- * same scan run over the chunks in reverse order on (Z, dO) from a zero state,
- * so each S_c is a sum of its own terms, never a difference of prefix sums.
+ * The states W_c are W_states [B, k, d, f] dtype when given (kept by the
+ * forward call through ttt_layer_options.W_states; DEVICE, 16-byte aligned),
+ * else recomputed by the chunk scan (NULL).  The suffixes come from the same
+ * scan run over the chunks in reverse order on (Z, dO) from a zero state, so
+ * each S_c is a sum of its own terms, never a difference of prefix sums.
  * With bf16 the states W_c and S_c are held in bf16 (fp32 accumulation), as in
  * the forward call.  Rows are single documents starting at W_down0 (no
  * document starts, resumed state or update mask).  Inputs as in
@@ -206,8 +226,8 @@ int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype,
  * gives dW_down0 = 0 and touches nothing else.  Errors as for every entry
  * point (a too small workspace: TTT_ERR_WORKSPACE). */
 int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
-                      const void* W_down0, const void* dO, void* dZ, void* dVhat, float* dW_down0,
-                      void* workspace, size_t workspace_bytes, void* stream);
+                      const void* W_down0, const void* dO, const void* W_states, void* dZ, void* dVhat,
+                      float* dW_down0, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- the individual steps (each is one stage of the call above; they compose
  *      into it and exist for composition and per-step checks).  The updates

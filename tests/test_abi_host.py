@@ -194,45 +194,69 @@ def test_step_entry_points_validate():
 
 
 def test_backward_workspace_and_validation():
-    """ttt_core_backward's workspace: eta V^ (row-major), the recomputed states and the suffix states (dtype), the rows' fp32
-    totals, a zero start state, and the scans' own scratch: segment partials for the fused scan (which reads Z, V^
-    and dO as they are); token-contiguous copies of Z and dO in reverse chunk order, of Z in order, and fp32
-    per-chunk deltas for the delta + scan path."""
+    """ttt_core_backward's workspace: eta V^ (row-major), the recomputed states (unless the caller keeps them) and
+    the suffix states (dtype), the rows' fp32 totals, a zero start state, and the scans' own scratch: segment
+    partials for the fused scan (which reads Z, V^ and dO as they are); token-contiguous copies of Z, of V^, of
+    Z and dO in reverse chunk order, and fp32 per-chunk deltas for the delta + scan path."""
     lib = cw.lib()
     al = lambda x: (x + 255) // 256 * 256
     out = ctypes.c_size_t(0)
 
-    def ws(B, n, d, f, C, dtype=cw.TTT_BF16):
-        st = lib.ttt_core_backward_workspace_bytes(ctypes.byref(cw.InplaceShape(B, n, d, f, C, 1)), dtype,
+    def ws(B, n, d, f, C, dtype=cw.TTT_BF16, saved=0):
+        st = lib.ttt_core_backward_workspace_bytes(ctypes.byref(cw.InplaceShape(B, n, d, f, C, 1)), dtype, saved,
                                                    ctypes.byref(out))
         return st, out.value
 
     B, n, d, f, C = 2, 2048, 256, 512, 256      # fused, four segments (as the forward plan of this shape)
     k, e = n // C, 2
-    base = al(B * n * d * e) + 2 * al(B * k * d * f * e) + al(B * d * f * 4) + al(d * f * e)
-    assert ws(B, n, d, f, C) == (cw.TTT_OK, base + al(B * (k - k // 4) * d * f * e) + al(B * 3 * d * f * 4))
+    states = al(B * k * d * f * e)
+    base = al(B * n * d * e) + states + al(B * d * f * 4) + al(d * f * e)
+    seg = al(B * (k - k // 4) * d * f * e) + al(B * 3 * d * f * 4)
+    assert ws(B, n, d, f, C) == (cw.TTT_OK, base + states + seg)
+    assert ws(B, n, d, f, C, saved=1) == (cw.TTT_OK, base + seg)
     # chunk 40: not on the 64-token step of the fused scan, so per-chunk fp32 deltas
     n2, C2 = 2000, 40
     k2 = n2 // C2
-    base2 = al(B * n2 * d * e) + 2 * (al(B * n2 * f * e) + al(B * n2 * d * e)) + 2 * al(B * k2 * d * f * e) + \
+    base2 = al(B * n2 * d * e) + 2 * (al(B * n2 * d * e) + al(B * n2 * f * e)) + 2 * al(B * k2 * d * f * e) + \
         al(B * d * f * 4) + al(d * f * e)
     assert ws(B, n2, d, f, C2) == (cw.TTT_OK, base2 + al(B * k2 * d * f * 4))
     assert ws(0, n, d, f, C) == (cw.TTT_OK, 0) and ws(B, 0, d, f, C) == (cw.TTT_OK, 0)
     assert ws(B, 2000, d, f, C)[0] == cw.TTT_ERR_SHAPE
-    assert lib.ttt_core_backward_workspace_bytes(ctypes.byref(cw.InplaceShape(B, n, d, f, C, 1)), cw.TTT_BF16,
+    assert lib.ttt_core_backward_workspace_bytes(ctypes.byref(cw.InplaceShape(B, n, d, f, C, 1)), cw.TTT_BF16, 0,
                                                  None) == cw.TTT_ERR_ARG
     s = cw.InplaceShape(B, n, d, f, C, 1)
     nb = ws(B, n, d, f, C)[1]
-    p6 = [_fake() for _ in range(6)]   # Z, Vhat, W_down0, dO, dZ, dVhat
-    call = lambda eta, ptrs, dW, w, nbytes: lib.ttt_core_backward(ctypes.byref(s), cw.TTT_BF16, eta, *ptrs, dW, w,
-                                                                    nbytes, None)
-    assert call(0.1, p6, _fake(), _fake(), nb - 1) == cw.TTT_ERR_WORKSPACE
-    assert call(0.1, p6, _fake(), None, nb) == cw.TTT_ERR_WORKSPACE
-    assert call(float("nan"), p6, _fake(), _fake(), nb) == cw.TTT_ERR_ARG
-    assert call(0.1, p6, None, _fake(), nb) == cw.TTT_ERR_ARG
-    assert call(0.1, [None] + p6[1:], _fake(), _fake(), nb) == cw.TTT_ERR_ARG
-    assert call(0.1, p6[:3] + [ctypes.c_void_p(0x100008)] + p6[4:], _fake(), _fake(), nb) == cw.TTT_ERR_ARG
-    assert lib.ttt_core_backward(ctypes.byref(s), 7, 0.1, *p6, _fake(), _fake(), nb, None) == cw.TTT_ERR_DTYPE
+    ins = [_fake() for _ in range(4)]    # Z, Vhat, W_down0, dO
+    outs = [_fake() for _ in range(2)]   # dZ, dVhat
+
+    def call(eta, ins, Ws, outs, dW, w, nbytes, dtype=cw.TTT_BF16):
+        return lib.ttt_core_backward(ctypes.byref(s), dtype, eta, *ins, Ws, *outs, dW, w, nbytes, None)
+
+    assert call(0.1, ins, None, outs, _fake(), _fake(), nb - 1) == cw.TTT_ERR_WORKSPACE
+    assert call(0.1, ins, None, outs, _fake(), None, nb) == cw.TTT_ERR_WORKSPACE
+    # kept states shrink the workspace by one set of states
+    assert call(0.1, ins, _fake(), outs, _fake(), _fake(), nb - states - 1) == cw.TTT_ERR_WORKSPACE
+    assert call(float("nan"), ins, None, outs, _fake(), _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, ins, None, outs, None, _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, [None] + ins[1:], None, outs, _fake(), _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, ins[:3] + [ctypes.c_void_p(0x100008)], None, outs, _fake(), _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, ins, ctypes.c_void_p(0x100008), outs, _fake(), _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, ins, None, outs, _fake(), _fake(), nb, dtype=7) == cw.TTT_ERR_DTYPE
+
+
+def test_forward_keeps_states_only_for_the_dot_objective():
+    lib = cw.lib()
+    s = cw.InplaceShape(1, 2048, 256, 512, 256, 4)
+    out = ctypes.c_size_t(0)
+    assert lib.ttt_inplace_workspace_bytes(ctypes.byref(s), cw.TTT_BF16, cw.TTT_MODE_MSE, 0,
+                                           ctypes.byref(out)) == cw.TTT_OK
+    opts = cw.LayerOptions(None, 0, None, None, _fake())
+    args = [_fake() for _ in range(3)]    # Z, Vhat, W_down0
+    assert lib.ttt_core_apply_update_ex(ctypes.byref(s), cw.TTT_BF16, cw.TTT_MODE_MSE, 0.1, *args, ctypes.byref(opts),
+                                        _fake(), _fake(), _fake(), out.value, None) == cw.TTT_ERR_ARG
+    opts = cw.LayerOptions(None, 0, None, None, ctypes.c_void_p(0x100004))
+    assert lib.ttt_core_apply_update_ex(ctypes.byref(s), cw.TTT_BF16, cw.TTT_MODE_DOT, 0.1, *args, ctypes.byref(opts),
+                                        _fake(), _fake(), _fake(), 1 << 40, None) == cw.TTT_ERR_ARG
 
 
 def test_lact_validation():

@@ -102,6 +102,43 @@ def test_backward_rows_independent():
     assert rel(f64(dW0), oracle(x, cfg)[2]) < TOL["bf16"]
 
 
+# the states the forward chunk loop keeps are the ones the backward recomputes, bit for bit (same operands, same
+# accumulation order), on the fused scan with segments, without, and on the delta + scan path
+@pytest.mark.parametrize("dtype,C,k", [("bf16", 128, 4), ("f32", 96, 3), ("bf16", 72, 2)])
+def test_backward_with_kept_states(dtype, C, k):
+    cfg = cfg_of(dtype, 2, k, C)
+    x = ti.backward_inputs(cfg)
+    g = {name: t.cuda() for name, t in x.items()}
+    B, n, d, f = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff
+    Ws = torch.full((B, k, d, f), float("nan"), dtype=g["Z"].dtype, device="cuda")
+    O, Wf = cw.ttt_core_apply_update(g["Z"], g["Vhat"], g["W_down0"], C, cfg.eta, "dot", W_states=Ws)
+    O0, Wf0 = cw.ttt_core_apply_update(g["Z"], g["Vhat"], g["W_down0"], C, cfg.eta, "dot")
+    kept = cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta, W_states=Ws)
+    again = cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O0) and torch.equal(Wf, Wf0)
+    assert all(torch.equal(a, b) for a, b in zip(kept, again))
+    assert torch.equal(Ws[:, 0], g["W_down0"].expand(B, d, f))      # chunk 0 is applied with W_down0
+    rZ, rV, rW = oracle(x, cfg)
+    assert rel(f64(kept[0]), rZ) < TOL[dtype] and rel(f64(kept[1]), rV) < TOL[dtype]
+
+
+def test_layer_keeps_states():
+    # the whole layer hands out the states it applied; its outputs do not change
+    cfg = ti.InplaceConfig("keep", 2, 1024, 264, 392, 256, 0.05, "dot", "bf16", seed=8)
+    g = {name: t.cuda() for name, t in ti.inplace_inputs(cfg).items()}
+    args = (g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"], g["conv_w"], cfg.chunk, cfg.eta)
+    Ws = torch.full((2, 4, 264, 392), float("nan"), dtype=torch.bfloat16, device="cuda")
+    O, Wf = cw.ttt_chunk_apply_update(*args, W_states=Ws)
+    O0, Wf0 = cw.ttt_chunk_apply_update(*args)
+    Zt = cw.ttt_produce_z(g["H"], g["W_gate"], g["W_up"], with_z=False)[1]
+    O1 = cw.ttt_chunk_apply(Zt, Ws, cfg.chunk)          # the kept states reproduce the outputs
+    torch.cuda.synchronize()
+    assert torch.equal(O, O0) and torch.equal(Wf, Wf0) and torch.equal(O1, O)
+    with pytest.raises(cw.TTTError):
+        cw.ttt_chunk_apply_update(*args[:-1], 0.5, "mse", W_states=Ws)
+
+
 def test_full_size_backward_sampled():
     """The 128K workload (131072 tokens, d 2560, d_ff 9728, chunk 4096).  The maps are separable: columns P of dZ
     and dW_down0 depend on columns P of Z and W_down0 only, and the last chunks' dVhat on those chunks alone (their
