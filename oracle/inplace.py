@@ -46,7 +46,7 @@ import numpy as np
 __all__ = [
     "silu", "causal_depthwise_conv1d", "forward_chunk_conv1d", "target_values", "gated_intermediate",
     "gated_mlp", "loss_dot", "loss_mse", "grad_dot", "grad_mse",
-    "chunk_apply_update", "chunk_core_backward", "chunk_prefix_form", "inplace_layer",
+    "chunk_apply_update", "chunk_core_backward", "chunk_prefix_form", "inplace_layer", "layer_backward",
 ]
 
 
@@ -285,3 +285,56 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
             W = W - eta * grad(W, Zc, Vc)
         W_final[b] = W
     return O, W_final
+
+
+def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, dO):
+    """Gradients of a loss that depends on the output O of the dot-objective
+    layer (inplace_layer with mode "dot", the causal convolution, one document
+    per row), given dO = dLoss/dO [B, n, d].  Returns (dH, dX0 [B, n, d],
+    dW_gate, dW_up [f, d], dW_down0 [d, f], dW_target [d, d], dconv_w [d, K]).
+
+    The chain rule through the layer's definitions, one step at a time:
+      * the chunk loop (chunk_core_backward, per row) gives dZ, dVhat and the
+        row's part of dW_down0;
+      * Z = silu(A) * U with A = H W_gate^T and U = H W_up^T (eq. (2)):
+        dA = dZ * U * silu'(A) and dU = dZ * silu(A), where
+        silu'(a) = s(a) (1 + a (1 - s(a))) with s the logistic function;
+        dW_gate = dA^T H, dW_up = dU^T H, dH = dA W_gate + dU W_up;
+      * Vhat = Y W_target with Y the causal convolution of X0 (eq. (5)):
+        dW_target = Y^T dVhat and dY = dVhat W_target^T;
+      * Y[t, i] = sum_j conv_w[i, j] X0[t - (K-1) + j, i]:
+        dconv_w[i, j] = sum_t dY[t, i] X0[t - (K-1) + j, i] and
+        dX0[s, i] = sum_j conv_w[i, j] dY[s + (K-1) - j, i] (rows outside
+        the sequence contribute nothing).
+    The weights are shared by the batch rows, so their gradients add over rows.
+    """
+    H, X0, Wg, Wu, W0, Wt, cw, dO = map(_f64, (H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO))
+    B, n, d = H.shape
+    K = cw.shape[1]
+    dH, dX0 = np.zeros_like(H), np.zeros_like(X0)
+    dWg, dWu = np.zeros_like(Wg), np.zeros_like(Wu)
+    dW0, dWt, dcw = np.zeros_like(W0), np.zeros_like(Wt), np.zeros_like(cw)
+    for b in range(B):
+        A = H[b] @ Wg.T
+        U = H[b] @ Wu.T
+        with np.errstate(over="ignore"):
+            sg = 1.0 / (1.0 + np.exp(-A))
+        Z = A * sg * U
+        Y = causal_depthwise_conv1d(X0[b], cw)
+        V = Y @ Wt
+        dZ, dV, dW0_b = chunk_core_backward(Z, V, W0, chunk, eta, dO[b])
+        dW0 += dW0_b
+        dA = dZ * U * (sg * (1.0 + A * (1.0 - sg)))
+        dU = dZ * (A * sg)
+        dWg += dA.T @ H[b]
+        dWu += dU.T @ H[b]
+        dH[b] = dA @ Wg + dU @ Wu
+        dWt += Y.T @ dV
+        dY = dV @ Wt.T
+        for j in range(K):
+            back = K - 1 - j              # tap j reads the token this many steps back
+            if back >= n:
+                continue
+            dcw[:, j] += np.sum(dY[back:] * X0[b, : n - back], axis=0)
+            dX0[b, : n - back] += cw[:, j] * dY[back:]
+    return dH, dX0, dWg, dWu, dW0, dWt, dcw

@@ -564,3 +564,54 @@ def test_core_backward_finite_differences():
             p[which][idx] += h
             m[which][idx] -= h
             assert abs((L(*p) - L(*m)) / (2 * h) - grad[idx]) < 1e-6 * max(1.0, abs(grad[idx]))
+
+
+def _torch_layer(H, X0, Wg, Wu, W0, Wt, cw, C, eta):
+    """The dot-objective layer written with torch float64 primitives (F.silu, grouped conv1d with left padding,
+    the chunk loop), for autograd."""
+    import torch.nn.functional as F
+    B, n, d = H.shape
+    K = cw.shape[1]
+    Z = F.silu(H @ Wg.T) * (H @ Wu.T)
+    Y = F.conv1d(F.pad(X0.transpose(1, 2), (K - 1, 0)), cw[:, None, :], groups=d).transpose(1, 2)
+    V = Y @ Wt
+    return torch.stack([_torch_dot_chunk_loop(Z[b], V[b], W0, C, eta) for b in range(B)])
+
+
+@pytest.mark.parametrize("n,C,K", [(12, 4, 3), (10, 5, 1), (9, 3, 4)])
+def test_layer_backward_matches_autograd(n, C, K):
+    """Every gradient of the whole dot layer (producers, causal conv, target projection, chunk loop) against torch
+    autograd of the same layer built from torch's own silu and grouped conv1d, two batch rows sharing the weights."""
+    rng = _rng(52)
+    B, d, f, eta = 2, 3, 5, 0.2
+    shapes = ((B, n, d), (B, n, d), (f, d), (f, d), (d, f), (d, d), (d, K))
+    H, X0, Wg, Wu, W0, Wt, cw = (rng.standard_normal(s) * 0.7 for s in shapes)
+    dO = rng.standard_normal((B, n, d))
+    ours = orc.layer_backward(H, X0, Wg, Wu, W0, Wt, cw, C, eta, dO)
+    ts = [torch.tensor(a, requires_grad=True) for a in (H, X0, Wg, Wu, W0, Wt, cw)]
+    (_torch_layer(*ts, C, eta) * torch.from_numpy(dO)).sum().backward()
+    for got, t in zip(ours, ts):
+        np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-11, atol=1e-11)
+    # the forward it differentiates is the oracle's own layer
+    O, _ = orc.inplace_layer(H, X0, Wg, Wu, W0, Wt, cw, C, eta, "dot")
+    np.testing.assert_allclose(O, _torch_layer(*[t.detach() for t in ts], C, eta).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_layer_backward_finite_differences():
+    """Central differences of <O, dO> through the oracle's layer for entries of the conv taps, W_target, W_gate and
+    X0 (the entries reached only through the producers and the convolution)."""
+    rng = _rng(53)
+    B, n, C, d, f, K, eta = 1, 8, 4, 2, 3, 3, 0.3
+    shapes = ((B, n, d), (B, n, d), (f, d), (f, d), (d, f), (d, d), (d, K))
+    args = [rng.standard_normal(s) * 0.7 for s in shapes]
+    dO = rng.standard_normal((B, n, d))
+    grads = orc.layer_backward(*args, C, eta, dO)
+    L = lambda a: float(np.sum(orc.inplace_layer(*a, C, eta, "dot")[0] * dO))
+    h = 1e-6
+    for which, idx in ((6, (1, 0)), (6, (0, 2)), (5, (1, 0)), (2, (2, 1)), (1, (0, 2, 1)), (1, (0, 7, 0))):
+        p = [a.copy() for a in args]
+        m = [a.copy() for a in args]
+        p[which][idx] += h
+        m[which][idx] -= h
+        g = grads[which][idx]
+        assert abs((L(p) - L(m)) / (2 * h) - g) < 1e-6 * max(1.0, abs(g)), (which, idx)
