@@ -61,6 +61,8 @@ _SIGNATURES = {
     "ttt_core_apply_update_ex": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P,
                                       ctypes.POINTER(LayerOptions), _P, _P, _P, _S, _P]),
     "ttt_core_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
+    "ttt_layer_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
+    "ttt_layer_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 17 + [_S, _P]),
     "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "ttt_produce_z": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P, _P]),
     "ttt_vhat_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, ctypes.POINTER(_S)]),
@@ -281,6 +283,46 @@ def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVh
                                    _stream(dev)),
            "ttt_core_backward")
     return dZ, dVhat, dW_down0
+
+
+def ttt_layer_backward_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, saved_states=False) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().ttt_layer_backward_workspace_bytes(ctypes.byref(shape), _dt(dtype), int(bool(saved_states)),
+                                                    ctypes.byref(n)),
+           "ttt_layer_backward_workspace_bytes")
+    return n.value
+
+
+def ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk: int, eta: float, W_states=None,
+                       grads=None, workspace=None):
+    """Gradients of the dot layer with respect to every input, given dO = dLoss/dO [B, n, d], with the per-chunk
+    states W_states kept by the forward call or recomputed (None).  Returns (dH, dX0, dW_gate, dW_up, dW_down0,
+    dW_target, dconv_w): activations in the inputs' dtype, weight gradients fp32 summed over the batch rows."""
+    B, n, d = H.shape
+    f = W_gate.shape[0]
+    K = conv_w.shape[1]
+    dt, dev = H.dtype, H.device
+    for name, t, shp in (("H", H, (B, n, d)), ("X0", X0, (B, n, d)), ("W_gate", W_gate, (f, d)),
+                         ("W_up", W_up, (f, d)), ("W_down0", W_down0, (d, f)), ("W_target", W_target, (d, d)),
+                         ("conv_w", conv_w, (d, K)), ("dO", dO, (B, n, d))):
+        _need(t, name, shp, dt, dev)
+    shapes = (((B, n, d), dt), ((B, n, d), dt), ((f, d), torch.float32), ((f, d), torch.float32),
+              ((d, f), torch.float32), ((d, d), torch.float32), ((d, K), torch.float32))
+    if grads is None:
+        grads = tuple(torch.empty(*shp, dtype=t, device=dev) for shp, t in shapes)
+    for g, (shp, t) in zip(grads, shapes):
+        _need(g, "gradient", shp, t, dev)
+    if W_states is not None:
+        _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
+    shape = _inplace_shape(B, n, d, f, chunk, K)
+    nbytes = ttt_layer_backward_workspace_bytes(shape, dt, W_states is not None)
+    ws = _workspace(nbytes, dev, workspace)
+    sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
+    _check(lib().ttt_layer_backward(ctypes.byref(shape), _dt(dt), float(eta), _ptr(H), _ptr(X0), _ptr(W_gate),
+                                    _ptr(W_up), _ptr(W_down0), _ptr(W_target), _ptr(conv_w), _ptr(dO), sp,
+                                    *[_ptr(g) for g in grads], _ptr(ws), nbytes, _stream(dev)),
+           "ttt_layer_backward")
+    return grads
 
 
 def ttt_produce_z(H, W_gate, W_up, Z=None, Zt=None, with_z=True):

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "launch.hpp"
 #include "ttt.h"
 
@@ -319,7 +321,7 @@ int bwd_scan(const BwdPlan& p, const T* Zt, const T* Vt, const T* W0, T* Wc, flo
 // sequences, and dW_down0 as the sum of the rows' totals.
 template <typename T>
 int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, const void* W0, const void* dOv,
-                  const void* Wsaved, void* dZ, void* dV, float* dW0, char* ws, hipStream_t s) {
+                  const void* Wsaved, void* dZ, void* dV, float* dW0, char* ws, hipStream_t s, bool vs_ready = false) {
   const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
   const int64_t df = (int64_t)d * f;
   if (p.B * p.n == 0) return dev(ttt::launch_zero<float>(dW0, df, s));
@@ -333,7 +335,7 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
   float* Tt = (float*)(ws + p.off_T);
   const T* Slast = Sr + (int64_t)(k - 1) * df;      // S_c = Sr[k - 1 - c]: stride -df from here
   int st = dev(ttt::launch_zero<T>(Z0, df, s));
-  if (st == TTT_OK) st = dev(ttt::launch_scale<T>(V, Vs, (int64_t)B * n * d, eta, s));
+  if (st == TTT_OK && !vs_ready) st = dev(ttt::launch_scale<T>(V, Vs, (int64_t)B * n * d, eta, s));
   if (p.fused) {
     // W_c (its W_final lands in Tt and is overwritten by the second scan)
     if (st == TTT_OK && !p.saved) st = bwd_scan<T>(p, Z, Vs, (const T*)W0, Wc, Tt, eta, false, ws, s);
@@ -359,6 +361,137 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
     st = dev(ttt::launch_dz<T>(dO, Vs, Wc, (int64_t)k * df, df, Slast, (int64_t)k * df, -df, (T*)dZ, B, n, d, f, C,
                                s));
   if (st == TTT_OK) st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
+  return st;
+}
+
+// ------------------------------------------------------------------ backward of the whole dot layer
+
+// Workspace of ttt_layer_backward: the recomputed Z and Y, W_target^T, the
+// chunk loop's backward (its own plan, whose eta V^ region is filled here), dZ,
+// dV^, G = [dA | dU], dY, the two token-contraction scans' scratch (sized for
+// the larger state, [2f, d] or [d, d]), and the tap-gradient partials.
+struct LayerBwdPlan {
+  BwdPlan core;
+  int64_t B, n, d, f, C, K;
+  size_t esz;
+  int kk;                       // chunks the weight-gradient scans are cut into (their segments divide it)
+  int S_gu, S_t;                // segments of the [dW_gate; dW_up] and dW_target scans
+  int64_t DFm, npart;
+  size_t off_Z, off_Y, off_WtT, off_dZ, off_dV, off_G, off_dY, off_wWc, off_wWp, off_wTot, off_wWf, off_wzero,
+      off_part, off_core, total;
+};
+
+int make_layer_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, LayerBwdPlan* p) {
+  *p = LayerBwdPlan{};
+  int st = make_bwd_plan(s, dtype, saved, &p->core);
+  if (st != TTT_OK) return st;
+  if (!p->core.fused) return TTT_ERR_UNSUPPORTED;     // the weight gradients take the fused scan's token steps
+  p->B = s->batch;
+  p->n = s->seq_len;
+  p->d = s->d_model;
+  p->f = s->d_ff;
+  p->C = s->chunk;
+  p->K = s->conv_k;
+  p->esz = p->core.esz;
+  const int64_t ks = kstep(dtype);
+  p->kk = p->n % (4 * ks) == 0 ? 4 : p->n % (2 * ks) == 0 ? 2 : 1;
+  const int64_t Cw = p->kk > 0 ? p->n / p->kk : 0;
+  p->S_gu = ttt::update_scan_segments(2 * p->f, p->d, p->kk, Cw);
+  p->S_t = ttt::update_scan_segments(p->d, p->d, p->kk, Cw);
+  p->DFm = std::max(2 * p->f * p->d, p->d * p->d);
+  p->npart = ttt::conv_bwd_partials(p->B * p->n);
+  if (p->B * p->n == 0) return TTT_OK;        // nothing but zero weight gradients
+  size_t off = 0;
+  auto take = [&](size_t* o, size_t bytes) {
+    *o = off;
+    off += align_up(bytes);
+  };
+  const size_t BN = (size_t)p->B * p->n, e = p->esz, DFm = (size_t)p->DFm, B = (size_t)p->B;
+  const int Smax = std::max(p->S_gu, p->S_t);
+  take(&p->off_Z, BN * p->f * e);
+  take(&p->off_Y, BN * p->d * e);
+  take(&p->off_WtT, (size_t)p->d * p->d * e);
+  take(&p->off_dZ, BN * p->f * e);
+  take(&p->off_dV, BN * p->d * e);
+  take(&p->off_G, BN * 2 * p->f * e);
+  take(&p->off_dY, BN * p->d * e);
+  take(&p->off_wWc, B * p->kk * DFm * e);
+  if (Smax > 1) {
+    take(&p->off_wWp, B * (p->kk - p->kk / Smax) * DFm * e);
+    take(&p->off_wTot, B * (Smax - 1) * DFm * 4);
+  }
+  take(&p->off_wWf, B * DFm * 4);
+  take(&p->off_wzero, DFm * e);
+  take(&p->off_part, (size_t)p->npart * p->d * p->K * 4);
+  take(&p->off_core, p->core.total);
+  p->total = off;
+  return TTT_OK;
+}
+
+// Sum over the rows and tokens of Q^T P (Q [B, n, dq], P [B, n, fp], row-major):
+// the fused update-scan from a zero state, its per-row totals in wWf [B, dq, fp].
+template <typename T>
+int token_contraction(const LayerBwdPlan& L, const T* P, const T* Q, int dq, int fp, int S, char* ws, hipStream_t s) {
+  const int B = (int)L.B, n = (int)L.n, Cw = (int)(L.n / L.kk);
+  return dev(ttt::launch_chunk_update_scan<T>(P, Q, (const T*)(ws + L.off_wzero), (T*)(ws + L.off_wWc),
+                                              (float*)(ws + L.off_wWf), (T*)(ws + L.off_wWp),
+                                              (float*)(ws + L.off_wTot), B, n, dq, fp, Cw, S, nullptr, nullptr, s,
+                                              ttt::kScanRowMajor));
+}
+
+template <typename T>
+int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void* X0v, const void* Wgv,
+                   const void* Wuv, const void* W0, const void* Wtv, const void* cwv, const void* dO,
+                   const void* Wsaved, void* dHv, void* dX0v, float* dWg, float* dWu, float* dW0, float* dWt,
+                   float* dcw, char* ws, hipStream_t s) {
+  const int B = (int)L.B, n = (int)L.n, d = (int)L.d, f = (int)L.f, C = (int)L.C, K = (int)L.K;
+  const int64_t rows = L.B * L.n, fd = (int64_t)f * d;
+  if (rows == 0) {
+    int st = dev(ttt::launch_zero<float>(dWg, fd, s));
+    if (st == TTT_OK) st = dev(ttt::launch_zero<float>(dWu, fd, s));
+    if (st == TTT_OK) st = dev(ttt::launch_zero<float>(dW0, fd, s));
+    if (st == TTT_OK) st = dev(ttt::launch_zero<float>(dWt, (int64_t)d * d, s));
+    if (st == TTT_OK) st = dev(ttt::launch_zero<float>(dcw, (int64_t)d * K, s));
+    return st;
+  }
+  const T* H = (const T*)Hv;
+  const T* Wg = (const T*)Wgv;
+  const T* Wu = (const T*)Wuv;
+  const T* Wt = (const T*)Wtv;
+  T* Z = (T*)(ws + L.off_Z);
+  T* Y = (T*)(ws + L.off_Y);
+  T* WtT = (T*)(ws + L.off_WtT);
+  T* dZ = (T*)(ws + L.off_dZ);
+  T* dV = (T*)(ws + L.off_dV);
+  T* G = (T*)(ws + L.off_G);
+  T* dY = (T*)(ws + L.off_dY);
+  float* wWf = (float*)(ws + L.off_wWf);
+  float* part = (float*)(ws + L.off_part);
+  char* cws = ws + L.off_core;
+  T* Vs = (T*)(cws + L.core.off_Vs);
+  // the forward's activations: Z (eq. (2)), Y = Conv1D(X0), eta V^ = eta Y W_target (eq. (5))
+  int st = dev(ttt::launch_zero<T>((T*)(ws + L.off_wzero), L.DFm, s));
+  if (st == TTT_OK) st = dev(ttt::launch_produce_z<T>(H, Wg, Wu, Z, nullptr, rows, n, d, f, s));
+  if (st == TTT_OK)
+    st = dev(ttt::launch_conv<T>((const T*)X0v, (const T*)cwv, Y, rows, n, d, K, nullptr, C, false, nullptr, s));
+  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Wt, WtT, 1, d, d, 1.0f, 0, s));
+  if (st == TTT_OK) st = dev(ttt::launch_apply<T>(Y, WtT, 0, 0, Vs, B, n, d, d, C, eta, s, true));
+  // the chunk loop: dZ, dV^ and dW_down0
+  if (st == TTT_OK) st = core_backward<T>(L.core, eta, Z, nullptr, W0, dO, Wsaved, dZ, dV, dW0, cws, s, true);
+  // the producer: [dA | dU], then [dW_gate; dW_up] = sum G^T H and dH = dA W_gate + dU W_up
+  if (st == TTT_OK) st = dev(ttt::launch_produce_z_bwd<T>(H, Wg, Wu, dZ, G, rows, n, d, f, s));
+  if (st == TTT_OK) st = token_contraction<T>(L, H, G, 2 * f, d, L.S_gu, ws, s);
+  if (st == TTT_OK) st = dev(ttt::launch_sum_rows(wWf, dWg, B, fd, s, 2 * fd));
+  if (st == TTT_OK) st = dev(ttt::launch_sum_rows(wWf + fd, dWu, B, fd, s, 2 * fd));
+  if (st == TTT_OK)
+    st = dev(ttt::launch_dz<T>(G + f, G, Wu, 0, 0, Wg, 0, 0, (T*)dHv, B, n, f, d, C, s, 2 * f));
+  // the target: dW_target = sum Y^T dV^, dY = dV^ W_target^T, then the convolution's taps and input
+  if (st == TTT_OK) st = token_contraction<T>(L, dV, Y, d, d, L.S_t, ws, s);
+  if (st == TTT_OK) st = dev(ttt::launch_sum_rows(wWf, dWt, B, (int64_t)d * d, s));
+  if (st == TTT_OK) st = dev(ttt::launch_apply<T>(dV, Wt, 0, 0, dY, B, n, d, d, C, 1.0f, s, true));
+  if (st == TTT_OK)
+    st = dev(ttt::launch_conv_bwd<T>((const T*)X0v, (const T*)cwv, dY, (T*)dX0v, part, rows, n, d, K, s));
+  if (st == TTT_OK) st = dev(ttt::launch_sum_rows(part, dcw, (int)L.npart, (int64_t)d * K, s));
   return st;
 }
 
@@ -485,6 +618,41 @@ int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, cons
   if (dtype == TTT_BF16)
     return core_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
   return core_backward<float>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
+}
+
+int ttt_layer_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states, size_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_ARG;
+  LayerBwdPlan p;
+  int st = make_layer_bwd_plan(shape, dtype, saved_states != 0, &p);
+  if (st != TTT_OK) return st;
+  *bytes = p.total;
+  return TTT_OK;
+}
+
+int ttt_layer_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
+                       const void* W_gate, const void* W_up, const void* W_down0, const void* W_target,
+                       const void* conv_w, const void* dO, const void* W_states, void* dH, void* dX0,
+                       float* dW_gate, float* dW_up, float* dW_down0, float* dW_target, float* dconv_w,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  LayerBwdPlan p;
+  int st = make_layer_bwd_plan(shape, dtype, W_states != nullptr, &p);
+  if (st != TTT_OK) return st;
+  if (!finite(eta)) return TTT_ERR_ARG;
+  if (!ok_ptr(dW_gate) || !ok_ptr(dW_up) || !ok_ptr(dW_down0) || !ok_ptr(dW_target) || !ok_ptr(dconv_w) ||
+      (W_states != nullptr && !aligned16(W_states)))
+    return TTT_ERR_ARG;
+  if (p.B * p.n > 0 && (!ok_ptr(H) || !ok_ptr(X0) || !ok_ptr(W_gate) || !ok_ptr(W_up) || !ok_ptr(W_down0) ||
+                        !ok_ptr(W_target) || !ok_ptr(conv_w) || !ok_ptr(dO) || !ok_ptr(dH) || !ok_ptr(dX0)))
+    return TTT_ERR_ARG;
+  if (p.total > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < p.total))
+    return TTT_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (dtype == TTT_BF16)
+    return layer_backward<bf16>(p, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, W_states, dH, dX0,
+                                dW_gate, dW_up, dW_down0, dW_target, dconv_w, ws, s);
+  return layer_backward<float>(p, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, W_states, dH, dX0,
+                               dW_gate, dW_up, dW_down0, dW_target, dconv_w, ws, s);
 }
 
 int ttt_produce_z(const ttt_inplace_shape* shape, int dtype, const void* H, const void* W_gate, const void* W_up,

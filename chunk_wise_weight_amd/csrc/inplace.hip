@@ -30,12 +30,15 @@ template <typename T> constexpr int esz() { return (int)sizeof(T); }
 
 // ------------------------------------------------------------------ conv, transpose
 
+// (the backward of the convolution follows k_conv below)
+
 // Y = CausalDepthwiseConv1D_KW(X0) (eq. (5) with the causal padding of §3):
 // Y[t, ch] = sum_j conv_w[ch, j] * X0[t - (KW-1) + j, ch], zero before the
 // sequence start.  One thread: RW consecutive rows x one 16-byte channel
 // chunk, reading each of the RW + KW - 1 input rows it needs once (a sliding
 // window; RW divides n, so a thread's rows never straddle a batch row).
 constexpr int kConvRows = 8;
+static_assert(kConvRows == kConvBwdRows, "the convolution's backward takes the forward's row groups");
 // FWD: the forward-looking in-chunk reading -- tap j multiplies the token j
 // steps ahead, and tokens past the chunk's end are zero (the review's
 // next-token example, Method §2); else tap KW - 1 is the current token.
@@ -113,6 +116,98 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
   }
 }
 
+// Backward of the causal convolution of k_conv (no document starts or halo):
+// dX0[s, ch] = sum_j conv_w[ch, j] dY[s + (KW-1) - j, ch], rows past the
+// sequence end zero; and dconv_w[ch, j] = sum_t dY[t, ch] X0[t - (KW-1) + j, ch],
+// rows before the sequence start zero.  One thread: one 16-byte channel chunk
+// over kConvBwdGroups groups of kConvRows rows (each group inside one batch
+// row), writing its share of dconv_w to part [blocks, d, KW] (fp32), which a
+// row sum then reduces.
+template <typename T, int KW>
+__global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ X0, const T* __restrict__ cw,
+                                                  const T* __restrict__ dY, T* __restrict__ dX0,
+                                                  float* __restrict__ part, int64_t rows, int n, int d) {
+  constexpr int V = Vec<T>::V, RW = kConvRows, NIN = RW + KW - 1;
+  const int nchunk = d / V;
+  const int64_t ngroups = rows / RW;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= conv_bwd_partials(rows) * nchunk) return;
+  const int ch = (int)(gid % nchunk) * V;
+  const int64_t pb = gid / nchunk;
+  float w[V][KW], gw[V][KW];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(cw + (int64_t)ch * KW);
+#pragma unroll
+    for (int c = 0; c < KW; ++c) {
+      const u32x4 x = src[c];
+      float fv[V];
+      if constexpr (sizeof(T) == 2) unpack8(x, fv);
+      else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fv[e] = __uint_as_float(x[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < V; ++e) w[(c * V + e) / KW][(c * V + e) % KW] = fv[e];
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int j = 0; j < KW; ++j) gw[v][j] = 0.f;
+  auto unpack = [](u32x4 x, float* o) {
+    if constexpr (sizeof(T) == 2) unpack8(x, o);
+    else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = __uint_as_float(x[e]);
+    }
+  };
+  for (int gi = 0; gi < kConvBwdGroups; ++gi) {
+    const int64_t grp = pb * kConvBwdGroups + gi;
+    if (grp >= ngroups) break;
+    const int64_t r0 = grp * RW;
+    const int pos0 = (int)(r0 % n);
+    // gy[i]: dY row r0 + i (zero from the sequence end on); xs[i]: X0 row r0 - (KW-1) + i (zero before the start)
+    u32x4 gy[NIN], xs[NIN];
+#pragma unroll
+    for (int i = 0; i < NIN; ++i) {
+      gy[i] = pos0 + i < n ? *reinterpret_cast<const u32x4*>(dY + (r0 + i) * d + ch) : u32x4{0u, 0u, 0u, 0u};
+      xs[i] = pos0 + i - (KW - 1) >= 0 ? *reinterpret_cast<const u32x4*>(X0 + (r0 + i - (KW - 1)) * d + ch)
+                                       : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      float o[V], g[V];
+#pragma unroll
+      for (int v = 0; v < V; ++v) o[v] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KW; ++j) {
+        float y[V], x[V];
+        unpack(gy[r + KW - 1 - j], y);
+        unpack(xs[r + j], x);
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v] = fmaf(w[v][j], y[v], o[v]);
+        if (j == 0) unpack(gy[r], g);
+#pragma unroll
+        for (int v = 0; v < V; ++v) gw[v][j] = fmaf(g[v], x[v], gw[v][j]);
+      }
+      u32x4 out;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = pack2_bf16(o[2 * e], o[2 * e + 1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = __float_as_uint(o[e]);
+      }
+      *reinterpret_cast<u32x4*>(dX0 + (r0 + r) * d + ch) = out;
+    }
+  }
+  float* pp = part + (pb * d + ch) * KW;
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+#pragma unroll
+    for (int j = 0; j < KW; ++j) pp[v * KW + j] = gw[v][j];
+}
+
 // dst[b][c][r] = scale * src[b][r][c] for an R x C matrix per batch entry (64 x 64 tiles).
 // rev > 0: the rows come in blocks of rev (chunks) whose order is reversed in
 // dst, i.e. r lands at column (R / rev - 1 - r / rev) rev + r % rev.
@@ -183,7 +278,7 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z(const T* __restrict__ H, const T* __restr
 
   // Zt [b, j, t]: staged as [128 columns][256 tokens]; a 16-byte piece holds
   // 8 (bf16) or 4 (fp32) tokens, which never straddle a batch row (n % 8 == 0).
-  {
+  if (Zt != nullptr) {
     const Staged<T, G::BP> st{smem};
 #pragma unroll
     for (int i = 0; i < G::NPB; ++i)
@@ -211,6 +306,70 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z(const T* __restrict__ H, const T* __restr
     sz.template flush<G::NT>(tn, [&](int r, int col) -> T* {
       return col < jn ? Z + (t0 + r) * f + j0 + col : nullptr;
     });
+  }
+}
+
+// Backward of the producer (eq. (2)) given dZ [rows, f]: the K loop recomputes
+// A = H W_gate^T and U = H W_up^T exactly as k_produce_z does, and the epilogue
+// forms dA = dZ U silu'(A) and dU = dZ silu(A), silu'(a) = s (1 + a (1 - s))
+// with s the logistic function, written as G [rows, 2f]: dA in columns
+// 0 .. f - 1, dU in f .. 2f - 1 (one matrix, so that one token contraction
+// gives both weight gradients).  dZ is read element by element: a lane's four
+// tokens at one column, 32 bytes of a row per 16 lanes.
+template <typename T>
+TTT_GEMM_KERNEL(Wide) void k_produce_z_bwd(const T* __restrict__ H, const T* __restrict__ Wg,
+                                           const T* __restrict__ Wu, const T* __restrict__ dZ, T* __restrict__ Gout,
+                                           int64_t rows, int n, int d, int f) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  const int TP = (int)((rows + G::BP - 1) / G::BP), TQ = (f + G::BQ / 2 - 1) / (G::BQ / 2);
+  int tp, tq;
+  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), TQ, TP, 8, tq, tp);
+  const int64_t t0 = (int64_t)tp * G::BP;
+  const int j0 = tq * (G::BQ / 2);
+  const uint64_t ldb = (uint64_t)d * esz<T>();
+
+  DmaOp<G::NW, G::BP> op;
+  op.init(H + t0 * d, nullptr, (int)min<int64_t>(G::BP, rows - t0), ldb, (unsigned)ldb);
+  DmaOp<G::NW, G::BQ, true> oq;
+  oq.init(Wg + (int64_t)j0 * d, Wu + (int64_t)j0 * d, min(G::BQ / 2, f - j0), ldb, (unsigned)ldb);
+  typename G::Frag acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
+
+  // block jj holds A, block jj + 2 the matching U (the layout of k_produce_z)
+  static_assert(G::NQB == 4 && G::BM == 16 && G::GPB == 1, "two gate/up block pairs per wave");
+  const int jl = (wave_id() % G::WQ) * 32 + (lane_id() & 15);
+  const int jn = min(G::BQ / 2, f - j0);
+  const int tn = (int)min<int64_t>(G::BP, rows - t0);
+#pragma unroll
+  for (int i = 0; i < G::NPB; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tr = G::acc_p(i, 0) + e, jc = jl + 16 * jj;
+        const float dz = (tr < tn && jc < jn) ? to_f32(dZ[(t0 + tr) * f + j0 + jc]) : 0.f;
+        const float a = acc[i][jj][e], u = acc[i][jj + 2][e], sg = sigmoid_f(a);
+        acc[i][jj][e] = dz * u * sg * (1.0f + a * (1.0f - sg));
+        acc[i][jj + 2][e] = dz * a * sg;
+      }
+  // dA, then dU: each staged as [256 tokens][128 columns] and written as whole rows of G
+  const int64_t ldg = 2 * (int64_t)f;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const Staged<T, G::BQ / 2> sz{smem};
+#pragma unroll
+    for (int i = 0; i < G::NPB; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sz.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj + 2 * half][e]);
+    __syncthreads();
+    sz.template flush<G::NT>(tn, [&](int r, int col) -> T* {
+      return col < jn ? Gout + (t0 + r) * ldg + (int64_t)half * f + j0 + col : nullptr;
+    });
+    __syncthreads();
   }
 }
 
@@ -651,10 +810,11 @@ struct Concat {
 // eta V^ and dO, [n, d]), K = d_model twice: one stream of K steps over
 // (S_j, eta V^_j), then (W_j, dO_j).  State j sits at W + b wsb + j wsc (S
 // likewise; its stride may be negative).  dZ [B, n, f] through LDS like O.
+// The rows of V and dO are ldq elements apart (d for [n, d] matrices).
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ V, const T* __restrict__ W,
                                 int64_t wsb, int64_t wsc, const T* __restrict__ S, int64_t ssb, int64_t ssc,
-                                T* __restrict__ dZ, int n, int d, int f, int C_) {
+                                T* __restrict__ dZ, int n, int d, int f, int C_, int ldq) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (f + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
@@ -676,8 +836,9 @@ TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ 
   Concat<DmaOp<G::NW, G::BQ>> oq;
   op.a.init(S + (int64_t)b * ssb + (int64_t)c * ssc + j0, min(G::BP, f - j0), ldf, d);
   op.b.init(W + (int64_t)b * wsb + (int64_t)c * wsc + j0, min(G::BP, f - j0), ldf, d);
-  oq.a.init(V + row0 * d, nullptr, min(G::BQ, C_ - t0), ldd, (unsigned)ldd);
-  oq.b.init(dO + row0 * d, nullptr, min(G::BQ, C_ - t0), ldd, (unsigned)ldd);
+  const uint64_t ldqb = (uint64_t)ldq * esz<T>();
+  oq.a.init(V + row0 * ldq, nullptr, min(G::BQ, C_ - t0), ldqb, (unsigned)ldd);
+  oq.b.init(dO + row0 * ldq, nullptr, min(G::BQ, C_ - t0), ldqb, (unsigned)ldd);
   op.n1 = oq.n1 = nks;
   mainloop<T, G>(op, oq, 2 * nks, acc, smem, NoHook{});
 
@@ -701,13 +862,14 @@ TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ 
   }
 }
 
-// out = sum over the B rows of Tot [B, df] (fp32), four elements per thread.
+// out [df] = sum over the B rows of Tot (fp32, rows `stride` elements apart),
+// four elements per thread.
 __global__ __launch_bounds__(256) void k_sum_rows(const float* __restrict__ Tot, float* __restrict__ out, int B,
-                                                  int64_t df) {
+                                                  int64_t df, int64_t stride) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= df) return;
   f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int b = 0; b < B; ++b) s += load4(Tot + (int64_t)b * df + e);
+  for (int b = 0; b < B; ++b) s += load4(Tot + (int64_t)b * stride + e);
   store4(out + e, s[0], s[1], s[2], s[3]);
 }
 
@@ -901,6 +1063,33 @@ hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int 
 }
 
 template <typename T>
+hipError_t launch_conv_bwd(const T* X0, const T* cw, const T* dY, T* dX0, float* part, int64_t rows, int n, int d,
+                           int K, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int64_t threads = conv_bwd_partials(rows) * (d / Vec<T>::V);
+  const dim3 g((unsigned)cdiv(threads, 256));
+  switch (K) {
+#define TTT_KW(KW)                                                                                            \
+  case KW:                                                                                                    \
+    k_conv_bwd<T, KW><<<g, 256, 0, s>>>(X0, cw, dY, dX0, part, rows, n, d);                                   \
+    break;
+    TTT_KW(1) TTT_KW(2) TTT_KW(3) TTT_KW(4) TTT_KW(5) TTT_KW(6) TTT_KW(7) TTT_KW(8)
+#undef TTT_KW
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_produce_z_bwd(const T* H, const T* Wg, const T* Wu, const T* dZ, T* G, int64_t rows, int n, int d,
+                                int f, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  k_produce_z_bwd<T><<<tiles_u(cdiv(rows, kWB) * cdiv(f, kWB / 2)), Wide::NT, 0, s>>>(H, Wg, Wu, dZ, G, rows, n, d,
+                                                                                      f);
+  return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int Cs, float scale, int rev, hipStream_t s) {
   if (batch == 0 || R == 0 || Cs == 0) return hipSuccess;
   k_transpose<T><<<dim3((unsigned)(cdiv(Cs, 64) * cdiv(R, 64)), (unsigned)batch), 256, 0, s>>>(src, dst, R, Cs, scale,
@@ -985,16 +1174,16 @@ hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_
 
 template <typename T>
 hipError_t launch_dz(const T* dO, const T* V, const T* W, int64_t wsb, int64_t wsc, const T* S, int64_t ssb,
-                     int64_t ssc, T* dZ, int B, int n, int d, int f, int Cs, hipStream_t s) {
+                     int64_t ssc, T* dZ, int B, int n, int d, int f, int Cs, hipStream_t s, int ldq) {
   const int64_t tiles = cdiv(f, kWB) * cdiv(Cs, kWB) * B * (n / Cs);
   if (tiles == 0) return hipSuccess;
-  k_dz<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(dO, V, W, wsb, wsc, S, ssb, ssc, dZ, n, d, f, Cs);
+  k_dz<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(dO, V, W, wsb, wsc, S, ssb, ssc, dZ, n, d, f, Cs, ldq > 0 ? ldq : d);
   return hipGetLastError();
 }
 
-hipError_t launch_sum_rows(const float* Tot, float* out, int B, int64_t df, hipStream_t s) {
+hipError_t launch_sum_rows(const float* Tot, float* out, int B, int64_t df, hipStream_t s, int64_t stride) {
   if (df == 0) return hipSuccess;
-  k_sum_rows<<<(unsigned)cdiv(df / 4, 256), 256, 0, s>>>(Tot, out, B, df);
+  k_sum_rows<<<(unsigned)cdiv(df / 4, 256), 256, 0, s>>>(Tot, out, B, df, stride > 0 ? stride : df);
   return hipGetLastError();
 }
 
@@ -1055,7 +1244,11 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
                                       hipStream_t, bool);                                                         \
   template hipError_t launch_scale<T>(const T*, T*, int64_t, float, hipStream_t);                                 \
   template hipError_t launch_dz<T>(const T*, const T*, const T*, int64_t, int64_t, const T*, int64_t, int64_t, T*, \
-                                   int, int, int, int, int, hipStream_t);                                         \
+                                   int, int, int, int, int, hipStream_t, int);                                    \
+  template hipError_t launch_produce_z_bwd<T>(const T*, const T*, const T*, const T*, T*, int64_t, int, int, int,  \
+                                              hipStream_t);                                                       \
+  template hipError_t launch_conv_bwd<T>(const T*, const T*, const T*, T*, float*, int64_t, int, int, int,        \
+                                         hipStream_t);                                                            \
   template hipError_t launch_zero<T>(T*, int64_t, hipStream_t);                                                   \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
                                           const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t); \

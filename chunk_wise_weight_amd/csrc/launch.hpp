@@ -65,11 +65,29 @@ template <typename T>
 hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_t s);
 // dZ_c = dO_c W_c + V_c S_c per chunk, V = eta V^ (backward of the dot chunk
 // loop); states W_c at W + b wsb + c wsc and S_c at S + b ssb + c ssc, [d, f].
+// The rows of V and dO are ldq elements apart (0: d).
 template <typename T>
 hipError_t launch_dz(const T* dO, const T* V, const T* W, int64_t wsb, int64_t wsc, const T* S, int64_t ssb,
-                     int64_t ssc, T* dZ, int B, int n, int d, int f, int C, hipStream_t s);
-// out [df] = sum over b of Tot [B, df] (fp32; df % 4 == 0).
-hipError_t launch_sum_rows(const float* Tot, float* out, int B, int64_t df, hipStream_t s);
+                     int64_t ssc, T* dZ, int B, int n, int d, int f, int C, hipStream_t s, int ldq = 0);
+// out [df] = sum over b of Tot [B rows, `stride` apart; stride 0: df] (fp32;
+// df and stride multiples of 4).
+hipError_t launch_sum_rows(const float* Tot, float* out, int B, int64_t df, hipStream_t s, int64_t stride = 0);
+// Backward of the producer: G [rows, 2f] = [dA | dU] from dZ [rows, f],
+// recomputing A = H W_gate^T and U = H W_up^T.
+template <typename T>
+hipError_t launch_produce_z_bwd(const T* H, const T* Wg, const T* Wu, const T* dZ, T* G, int64_t rows, int n, int d,
+                                int f, hipStream_t s);
+// Backward of the causal convolution: dX0 [rows, d] and the tap-gradient
+// partials part [conv_bwd_partials(rows), d, K] (fp32).
+template <typename T>
+hipError_t launch_conv_bwd(const T* X0, const T* cw, const T* dY, T* dX0, float* part, int64_t rows, int n, int d,
+                           int K, hipStream_t s);
+// Number of tap-gradient partials launch_conv_bwd writes: a thread takes
+// kConvBwdGroups groups of kConvBwdRows rows of one channel chunk.
+constexpr int kConvBwdRows = 8, kConvBwdGroups = 32;
+__host__ __device__ inline int64_t conv_bwd_partials(int64_t rows) {
+  return (rows / kConvBwdRows + kConvBwdGroups - 1) / kConvBwdGroups;
+}
 // p [n] = 0 (n % 4 == 0).
 template <typename T>
 hipError_t launch_zero(T* p, int64_t n, hipStream_t s);

@@ -159,3 +159,81 @@ def test_full_size_backward_sampled():
     _, rV, _ = orc.chunk_core_backward(ti.to_f64(Z[t0:]), V[t0:], W0, C, cfg.eta, dO[t0:])
     assert rel(dV[0][t0:], rV) < TOL["bf16"]
     assert np.all(np.isfinite(dZ)) and np.all(np.isfinite(dV))
+
+
+# ---------------------------------------------------------------- the whole layer
+
+GRAD_NAMES = ("dH", "dX0", "dW_gate", "dW_up", "dW_down0", "dW_target", "dconv_w")
+
+
+def layer_args(g):
+    return (g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"], g["conv_w"])
+
+
+def layer_case(dtype, B, n, C, K=4, d=264, f=392, eta=0.05, seed=41):
+    cfg = ti.InplaceConfig("lbwd", B, n, d, f, C, eta, "dot", dtype, conv_k=K, seed=seed)
+    x = ti.inplace_inputs(cfg)
+    dO = ti.backward_inputs(cfg.with_(seed=seed + 1))["dO"]
+    return cfg, x, dO
+
+
+@pytest.mark.parametrize("dtype,C,k,K", [("f32", 96, 3, 4), ("bf16", 128, 4, 4), ("bf16", 64, 3, 1), ("f32", 64, 4, 3)])
+def test_layer_backward_matches_oracle(dtype, C, k, K):
+    cfg, x, dO = layer_case(dtype, 2, k * C, C, K)
+    g = {name: t.cuda() for name, t in x.items()}
+    grads = cw.ttt_layer_backward(*layer_args(g), dO.cuda(), C, cfg.eta)
+    torch.cuda.synchronize()
+    ref = orc.layer_backward(*(ti.to_f64(x[name]) for name in ("H", "X0", "W_gate", "W_up", "W_down0", "W_target",
+                                                               "conv_w")), C, cfg.eta, ti.to_f64(dO))
+    for name, got, want in zip(GRAD_NAMES, grads, ref):
+        assert rel(f64(got), want) < TOL[dtype], name
+
+
+def test_layer_backward_with_kept_states():
+    # the layer's forward keeps its states; the backward given them agrees with the recomputing one
+    cfg, x, dO = layer_case("bf16", 2, 512, 128)
+    g = {name: t.cuda() for name, t in x.items()}
+    Ws = torch.empty(2, 4, cfg.d_model, cfg.d_ff, dtype=torch.bfloat16, device="cuda")
+    cw.ttt_chunk_apply_update(*layer_args(g), cfg.chunk, cfg.eta, W_states=Ws)
+    kept = cw.ttt_layer_backward(*layer_args(g), dO.cuda(), cfg.chunk, cfg.eta, W_states=Ws)
+    again = cw.ttt_layer_backward(*layer_args(g), dO.cuda(), cfg.chunk, cfg.eta)
+    torch.cuda.synchronize()
+    for name, a, b in zip(GRAD_NAMES, kept, again):
+        assert rel(f64(a), f64(b)) < 1e-2, name
+
+
+def test_layer_backward_empty_and_unsupported():
+    for B, n in ((0, 256), (2, 0)):
+        cfg, x, dO = layer_case("f32", B, n, 128)
+        g = {name: t.cuda() for name, t in x.items()}
+        grads = cw.ttt_layer_backward(*layer_args(g), dO.cuda(), 128, 0.05)
+        torch.cuda.synchronize()
+        assert all(not torch.any(t) for t in grads[2:])
+    cfg, x, dO = layer_case("bf16", 1, 240, 80)          # chunk 80: not on the fused scan's 64-token steps
+    g = {name: t.cuda() for name, t in x.items()}
+    with pytest.raises(cw.TTTError) as e:
+        cw.ttt_layer_backward(*layer_args(g), dO.cuda(), 80, 0.05)
+    assert e.value.status == cw.TTT_ERR_UNSUPPORTED
+
+
+def test_full_size_layer_backward_sampled():
+    """The 128K layer's backward.  Rows P of dW_gate and dW_up and columns P of dW_down0 depend on the rows P of
+    W_gate, W_up and the columns P of W_down0 alone (the chunk loop's states and suffixes are column-separable and
+    the target does not depend on them), so the oracle's layer backward on those 16 d_ff columns gives them exactly;
+    every other gradient must be finite."""
+    cfg = ti.workload("inplace_bf16_128k")
+    x = ti.inplace_inputs(cfg)
+    dO = ti.backward_inputs(ti.workload("inplace_bwd_bf16_128k"))["dO"]
+    g = {name: t.cuda() for name, t in x.items()}
+    grads = cw.ttt_layer_backward(*layer_args(g), dO.cuda(), cfg.chunk, cfg.eta)
+    torch.cuda.synchronize()
+    got = [f64(t) for t in grads]
+    del g, grads
+    P = np.sort(np.random.default_rng(6).choice(cfg.d_ff, 16, replace=False))
+    f = lambda name: ti.to_f64(x[name])
+    ref = orc.layer_backward(f("H"), f("X0"), f("W_gate")[P], f("W_up")[P], f("W_down0")[:, P], f("W_target"),
+                             f("conv_w"), cfg.chunk, cfg.eta, ti.to_f64(dO))
+    assert rel(got[2][P], ref[2]) < TOL["bf16"]
+    assert rel(got[3][P], ref[3]) < TOL["bf16"]
+    assert rel(got[4][:, P], ref[4]) < TOL["bf16"]
+    assert all(np.all(np.isfinite(t)) for t in got)
