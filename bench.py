@@ -145,7 +145,28 @@ def bench_generic(cfg, steps, warmup):
     import chunk_wise_weight_amd as cw
     import ttt_inputs as ti
 
-    if getattr(cfg, "backward", False):
+    if getattr(cfg, "layer_backward", False):
+        x = ti.inplace_inputs(cfg)
+        g = {k: v.cuda() for k, v in x.items()}
+        dO = ti.backward_inputs(cfg.with_(seed=cfg.seed + 3))["dO"].cuda()
+        B, n, d, f, K = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff, cfg.conv_k
+        dt = g["H"].dtype
+        w = (g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"], g["conv_w"])
+        Ws = None
+        if cfg.kept_states:
+            # the forward layer keeps its states (before the timed region, like the other inputs)
+            Ws = torch.empty(B, n // cfg.chunk, d, f, dtype=dt, device="cuda")
+            cw.ttt_chunk_apply_update(*w, cfg.chunk, cfg.eta, W_states=Ws)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        grads = tuple(torch.empty(*shp, dtype=t, device="cuda") for shp, t in (
+            ((B, n, d), dt), ((B, n, d), dt), ((f, d), torch.float32), ((f, d), torch.float32),
+            ((d, f), torch.float32), ((d, d), torch.float32), ((d, K), torch.float32)))
+        shape = cw.InplaceShape(B, n, d, f, cfg.chunk, K)
+        nbytes = cw.ttt_layer_backward_workspace_bytes(shape, dt, cfg.kept_states)
+        ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
+        call = lambda: cw.ttt_layer_backward(*w, dO, cfg.chunk, cfg.eta, W_states=Ws, grads=grads, workspace=ws)
+    elif getattr(cfg, "backward", False):
         x = ti.backward_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
         B, n, d, f = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff
@@ -228,6 +249,14 @@ def cpu_baseline(cfg, target_s):
                                                    if cfg.token_rates else None),
                                           loss=cfg.loss, weight_norm=cfg.weight_norm, use_muon=cfg.muon)
         per_tok_heads = 1
+    elif cfg.layer_backward:
+        x = ti.inplace_inputs(cfg)
+        ws = {k: ti.to_f64(x[k]) for k in ("W_gate", "W_up", "W_down0", "W_target", "conv_w")}
+        dO = ti.backward_inputs(cfg.with_(seed=cfg.seed + 3))["dO"]
+        run = lambda kc: orc.layer_backward(ti.to_f64(x["H"][:1, : kc * cfg.chunk]),
+                                            ti.to_f64(x["X0"][:1, : kc * cfg.chunk]), ws["W_gate"], ws["W_up"],
+                                            ws["W_down0"], ws["W_target"], ws["conv_w"], cfg.chunk, cfg.eta,
+                                            ti.to_f64(dO[:1, : kc * cfg.chunk]))
     elif cfg.backward:
         x = ti.backward_inputs(cfg)
         W0 = ti.to_f64(x["W_down0"])
@@ -317,9 +346,13 @@ def main():
             out["config"]["pass"] = "backward of the chunk loop (dZ, dVhat, dW_down0 from dLoss/dO)"
             out["config"]["states"] = "kept by the forward call" if cfg.kept_states else "recomputed"
             out["metric"] = "TTT chunk-loop backward tokens/s at 128K ctx; % of bf16 MFMA peak"
+        if cfg.layer_backward:
+            out["config"]["pass"] = "backward of the whole layer (every input and weight gradient from dLoss/dO)"
+            out["config"]["states"] = "kept by the forward call" if cfg.kept_states else "recomputed"
+            out["metric"] = "TTT-layer backward tokens/s at 128K ctx; % of bf16 MFMA peak"
 
     if (not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot" and cfg.docs == 1 and not cfg.conv_forward and
-            cfg.pieces == 1 and not cfg.backward):
+            cfg.pieces == 1 and not cfg.backward and not cfg.layer_backward):
         wall, per, _ = bench_inplace_dot(cfg, args.steps, args.warmup)
         fl, by = kernel_flops(cfg), kernel_bytes(cfg, 2 if dtype == "bf16" else 4)
         kern = {}

@@ -342,6 +342,24 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z_bwd(const T* __restrict__ H, const T* __r
   const int jl = (wave_id() % G::WQ) * 32 + (lane_id() & 15);
   const int jn = min(G::BQ / 2, f - j0);
   const int tn = (int)min<int64_t>(G::BP, rows - t0);
+  const int64_t ldg = 2 * (int64_t)f;
+  // bf16: the dZ tile [256 tokens][128 columns] (64 KB) comes into the first
+  // half of the LDS with 16-byte loads, dA is staged in the second half while
+  // it is read, and dU then replaces it.  fp32 (128 KB tiles): dZ is read from
+  // memory element by element and the two results share the LDS in turn.
+  constexpr bool kStageDz = sizeof(T) == 2;
+  constexpr int kHalf = G::BP * (G::BQ / 2) * (int)sizeof(T);
+  const Staged<T, G::BQ / 2> sdz{smem}, sda{smem + (kStageDz ? kHalf : 0)};
+  if constexpr (kStageDz) {
+    constexpr int PPR = (G::BQ / 2) * (int)sizeof(T) / 16;          // 16-byte pieces per row
+    for (int idx = threadIdx.x; idx < tn * PPR; idx += G::NT) {
+      const int r = idx / PPR, c = (idx - r * PPR) * (16 / (int)sizeof(T));
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (c < jn) v = *reinterpret_cast<const u32x4*>(dZ + (t0 + r) * f + j0 + c);
+      *reinterpret_cast<u32x4*>(smem + sdz.off(r, c)) = v;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
@@ -349,28 +367,39 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z_bwd(const T* __restrict__ H, const T* __r
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int tr = G::acc_p(i, 0) + e, jc = jl + 16 * jj;
-        const float dz = (tr < tn && jc < jn) ? to_f32(dZ[(t0 + tr) * f + j0 + jc]) : 0.f;
+        float dz;
+        if constexpr (kStageDz) dz = tr < tn ? to_f32(*reinterpret_cast<const T*>(smem + sdz.off(tr, jc))) : 0.f;
+        else dz = (tr < tn && jc < jn) ? to_f32(dZ[(t0 + tr) * f + j0 + jc]) : 0.f;
         const float a = acc[i][jj][e], u = acc[i][jj + 2][e], sg = sigmoid_f(a);
-        acc[i][jj][e] = dz * u * sg * (1.0f + a * (1.0f - sg));
-        acc[i][jj + 2][e] = dz * a * sg;
+        const float da = dz * u * sg * (1.0f + a * (1.0f - sg));
+        acc[i][jj + 2][e] = dz * a * sg;                 // dU
+        if constexpr (kStageDz) sda.put1(tr, jc, da);
+        else acc[i][jj][e] = da;
       }
-  // dA, then dU: each staged as [256 tokens][128 columns] and written as whole rows of G
-  const int64_t ldg = 2 * (int64_t)f;
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const Staged<T, G::BQ / 2> sz{smem};
+  if constexpr (!kStageDz) {
 #pragma unroll
     for (int i = 0; i < G::NPB; ++i)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sz.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj + 2 * half][e]);
-    __syncthreads();
-    sz.template flush<G::NT>(tn, [&](int r, int col) -> T* {
-      return col < jn ? Gout + (t0 + r) * ldg + (int64_t)half * f + j0 + col : nullptr;
-    });
-    __syncthreads();
+        for (int e = 0; e < 4; ++e) sda.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj][e]);
   }
+  __syncthreads();
+  // dA out as whole rows of G; then dU staged over the dZ tile (read by all waves before the barrier above)
+  sda.template flush<G::NT>(tn, [&](int r, int col) -> T* {
+    return col < jn ? Gout + (t0 + r) * ldg + j0 + col : nullptr;
+  });
+  if constexpr (!kStageDz) __syncthreads();
+#pragma unroll
+  for (int i = 0; i < G::NPB; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sdz.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj + 2][e]);
+  __syncthreads();
+  sdz.template flush<G::NT>(tn, [&](int r, int col) -> T* {
+    return col < jn ? Gout + (t0 + r) * ldg + f + j0 + col : nullptr;
+  });
 }
 
 // Vt = scale * (Y W_target)^T with WtT = W_target^T [d_out, d_in].  P = tokens,

@@ -61,6 +61,7 @@ class InplaceConfig:
     pieces: int = 1      # the sequence processed in this many calls, each resuming the previous one
     backward: bool = False   # the workload is the backward of the dot chunk loop (inputs Z, Vhat, W_down0, dO)
     kept_states: bool = False   # backward: the forward call kept its per-chunk states (no recompute)
+    layer_backward: bool = False   # the backward of the whole layer (inputs of the layer and dO)
     var_z: float = 0.356     # backward inputs: Z, the gated intermediate
     var_vhat: float = 1.0    # backward inputs: the target
     var_dout: float = 1.0    # backward inputs: the upstream gradient dLoss/dO
@@ -89,8 +90,13 @@ class InplaceConfig:
         """Algorithmic flops of one layer call: producer 4df, target 2d^2 + 2Kd,
         update 2df, apply 2df per token.  Backward of the chunk loop: 10df per
         token (the states' scan, the suffixes' scan, dVhat, and dZ's two
-        contractions, 2df each); 8df with the states kept by the forward call."""
+        contractions, 2df each); 8df with the states kept by the forward call.
+        Backward of the whole layer: that, plus the producer's recompute and
+        its backward (4df each), the gate and up weight gradients (4df), dH
+        (4df), and eta V^, dW_target and dY (2d^2 each)."""
         d, f, K = self.d_model, self.d_ff, self.conv_k
+        if self.layer_backward:
+            return float(self.tokens) * ((24.0 if self.kept_states else 26.0) * d * f + 6.0 * d * d)
         if self.backward:
             return float(self.tokens) * (8.0 if self.kept_states else 10.0) * d * f
         return float(self.tokens) * (8.0 * d * f + 2.0 * d * d + 2.0 * K * d)
@@ -175,6 +181,12 @@ WORKLOADS = {
     # the same with the per-chunk states kept by the forward call (no recompute)
     "inplace_bwd_bf16_128k_kept": InplaceConfig("inplace_bwd_bf16_128k_kept", 1, 131072, 2560, 9728, 4096, 0.01, "dot",
                                                 "bf16", seed=1005, backward=True, kept_states=True),
+    # the backward of the whole 128K layer (gradients of every input and weight from dLoss/dO)
+    "inplace_layer_bwd_bf16_128k": InplaceConfig("inplace_layer_bwd_bf16_128k", 1, 131072, 2560, 9728, 4096, 0.01, "dot",
+                                                 "bf16", seed=1002, layer_backward=True),
+    "inplace_layer_bwd_bf16_128k_kept": InplaceConfig("inplace_layer_bwd_bf16_128k_kept", 1, 131072, 2560, 9728, 4096,
+                                                      0.01, "dot", "bf16", seed=1002, layer_backward=True,
+                                                      kept_states=True),
     "mse_bf16_4x64k": InplaceConfig("mse_bf16_4x64k", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16", seed=1003),
     "lact_bf16_256k": LactConfig("lact_bf16_256k", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004),
     # the LaCT review's own update: dot-product loss, per-token learning rates, L2 weight normalisation
