@@ -221,7 +221,8 @@ def chunk_prefix_form(Z, Vhat, W0, chunk, eta):
 
 
 def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
-                  mode, max_chunks=None, x0_halo=None, doc_starts=None, conv_forward=False, W_init=None):
+                  mode, max_chunks=None, x0_halo=None, doc_starts=None, conv_forward=False, W_init=None,
+                  update_mask=None):
     """The whole In-Place TTT layer, one document per batch row.
 
     H, X0 [B, n, d]; W_gate, W_up [f, d]; W_down0 [d, f]; W_target [d, d];
@@ -242,6 +243,11 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
     `conv_forward` takes the forward-looking in-chunk convolution
     (forward_chunk_conv1d) for the target; it reads no row outside the chunk,
     so `x0_halo` and document starts do not change it.
+
+    `update_mask` [B, n_chunks] (truthy entries), if given, takes the update
+    step on the flagged chunks only; every chunk is applied (the strided
+    update of the LaCT review's section on the order of the apply and update
+    operations, read onto this layer).
 
     `max_chunks` stops after that many chunks (O then covers only those rows
     and W_final is the state after them) -- used to time a bounded sample.
@@ -282,7 +288,8 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
             Vc = Y @ W_target
             Zc = gated_intermediate(H[b, s:e], W_gate, W_up)
             O[b, s:e] = Zc @ W.T
-            W = W - eta * grad(W, Zc, Vc)
+            if update_mask is None or update_mask[b][c]:
+                W = W - eta * grad(W, Zc, Vc)
         W_final[b] = W
     return O, W_final
 

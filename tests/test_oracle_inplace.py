@@ -615,3 +615,61 @@ def test_layer_backward_finite_differences():
         m[which][idx] -= h
         g = grads[which][idx]
         assert abs((L(p) - L(m)) / (2 * h) - g) < 1e-6 * max(1.0, abs(g)), (which, idx)
+
+
+def _masked_dual_form_dot(Z, V, W0, C, eta, mask):
+    """The dual form above with the update mask: token s of an earlier chunk contributes only if its chunk is
+    flagged."""
+    n, f = Z.shape
+    d = V.shape[1]
+    O = np.zeros((n, d))
+    for t in range(n):
+        for i in range(d):
+            O[t, i] = sum(Z[t, j] * W0[i, j] for j in range(f))
+        for s in range(n):
+            if s // C < t // C and mask[s // C]:
+                dot = sum(Z[t, j] * Z[s, j] for j in range(f))
+                for i in range(d):
+                    O[t, i] += eta * dot * V[s, i]
+    return O
+
+
+def test_update_mask_dot_equals_masked_brute_force():
+    """The layer with an update mask (dot objective) against the token-level dual form in which only flagged
+    chunks' tokens reach later outputs; an all-ones mask is the unmasked layer."""
+    rng = _rng(60)
+    B, n, C, d, f, K, eta = 2, 12, 3, 3, 4, 2, 0.2
+    H, X0 = rng.standard_normal((B, n, d)), rng.standard_normal((B, n, d))
+    Wg, Wu = rng.standard_normal((f, d)) * 0.5, rng.standard_normal((f, d)) * 0.5
+    W0, Wt, cw = rng.standard_normal((d, f)), rng.standard_normal((d, d)), rng.standard_normal((d, K))
+    mask = np.array([[1, 0, 1, 0], [0, 1, 1, 0]], dtype=np.uint8)
+    O, _ = orc.inplace_layer(H, X0, Wg, Wu, W0, Wt, cw, C, eta, "dot", update_mask=mask)
+    for b in range(B):
+        Z = orc.gated_intermediate(H[b], Wg, Wu)
+        V = orc.target_values(X0[b], cw, Wt)
+        np.testing.assert_allclose(O[b], _masked_dual_form_dot(Z, V, W0, C, eta, mask[b]), rtol=1e-12, atol=1e-12)
+    O1, W1 = orc.inplace_layer(H, X0, Wg, Wu, W0, Wt, cw, C, eta, "dot", update_mask=np.ones((B, 4)))
+    O2, W2 = orc.inplace_layer(H, X0, Wg, Wu, W0, Wt, cw, C, eta, "dot")
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(W1, W2)
+
+
+def test_update_mask_mse_equals_resumed_calls_with_a_frozen_chunk():
+    """A masked chunk of the MSE layer is the same as resuming the sequence at that chunk with eta = 0 for one chunk
+    and then resuming again with the original eta (resumed calls are pinned separately)."""
+    rng = _rng(61)
+    B, C, d, f, K, eta = 1, 4, 3, 4, 3, 0.3
+    n = 3 * C
+    H, X0 = rng.standard_normal((B, n, d)), rng.standard_normal((B, n, d))
+    Wg, Wu = rng.standard_normal((f, d)) * 0.5, rng.standard_normal((f, d)) * 0.5
+    W0, Wt, cw = rng.standard_normal((d, f)), rng.standard_normal((d, d)), rng.standard_normal((d, K))
+    O, W = orc.inplace_layer(H, X0, Wg, Wu, W0, Wt, cw, C, eta, "mse", update_mask=np.array([[1, 0, 1]]))
+    piece = lambda a, c0, c1: a[:, c0 * C: c1 * C]
+    halo = lambda c0: X0[:, c0 * C - (K - 1): c0 * C]
+    Oa, Wa = orc.inplace_layer(piece(H, 0, 1), piece(X0, 0, 1), Wg, Wu, W0, Wt, cw, C, eta, "mse")
+    Ob, Wb = orc.inplace_layer(piece(H, 1, 2), piece(X0, 1, 2), Wg, Wu, W0, Wt, cw, C, 0.0, "mse", W_init=Wa,
+                               x0_halo=halo(1))
+    Oc, Wc = orc.inplace_layer(piece(H, 2, 3), piece(X0, 2, 3), Wg, Wu, W0, Wt, cw, C, eta, "mse", W_init=Wb,
+                               x0_halo=halo(2))
+    np.testing.assert_allclose(O, np.concatenate([Oa, Ob, Oc], axis=1), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(W, Wc, rtol=1e-12, atol=1e-12)
