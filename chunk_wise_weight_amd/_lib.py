@@ -28,7 +28,7 @@ class InplaceShape(ctypes.Structure):
 
 class LayerOptions(ctypes.Structure):
     _fields_ = [("doc_starts", ctypes.c_void_p), ("conv_forward", ctypes.c_int), ("W_init", ctypes.c_void_p),
-                ("x0_halo", ctypes.c_void_p), ("W_states", ctypes.c_void_p)]
+                ("x0_halo", ctypes.c_void_p), ("W_states", ctypes.c_void_p), ("update_mask", ctypes.c_void_p)]
 
 
 class LactOptions(ctypes.Structure):
@@ -149,6 +149,16 @@ def _inplace_shape(B, n, d, f, chunk, K) -> InplaceShape:
     return InplaceShape(int(B), int(n), int(d), int(f), int(chunk), int(K))
 
 
+def _flags(t, name, shape, dev):
+    """A per-chunk flag tensor (bool or uint8, device) as uint8, or None."""
+    if t is None:
+        return None
+    if t.dtype == torch.bool:
+        t = t.to(torch.uint8)
+    _need(t, name, shape, torch.uint8, dev)
+    return t
+
+
 def ttt_inplace_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, mode="dot", with_producers=True) -> int:
     out = ctypes.c_size_t(0)
     _check(lib().ttt_inplace_workspace_bytes(ctypes.byref(shape), _dt(dtype), _mode(mode), int(bool(with_producers)),
@@ -166,14 +176,15 @@ def _workspace(nbytes: int, device, workspace):
 
 def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk: int, eta: float, mode="dot",
                            O=None, W_final=None, workspace=None, doc_starts=None, conv_forward=False, W_init=None,
-                           x0_halo=None, W_states=None):
+                           x0_halo=None, W_states=None, update_mask=None):
     """The whole In-Place layer.  Returns (O [B, n, d], W_final [B, d, f] fp32).
 
     Options (ttt_chunk_apply_update_ex): doc_starts, a uint8 (or bool) device tensor [B, seq_len // chunk] whose
     nonzero entries mark the chunks that start a new document in their row; conv_forward, the forward-looking
     in-chunk convolution for the target; W_init [B, d, f] fp32 and x0_halo [B, K-1, d] to resume rows from an
     earlier call (its W_final and its last K-1 rows of X0); W_states [B, seq_len // chunk, d, f] (dtype) to keep
-    the per-chunk states of the dot objective for ttt_core_backward."""
+    the per-chunk states of the dot objective for ttt_core_backward; update_mask, a uint8 (or bool) device tensor
+    [B, seq_len // chunk] whose zero entries mark chunks that are applied without updating the state."""
     B, n, d = H.shape
     f = W_gate.shape[0]
     K = conv_w.shape[1]
@@ -195,7 +206,9 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
         _need(x0_halo, "x0_halo", (B, K - 1, d), dt, dev)
     if W_states is not None:
         _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
-    if doc_starts is None and not conv_forward and W_init is None and x0_halo is None and W_states is None:
+    update_mask = _flags(update_mask, "update_mask", (B, n // chunk if chunk > 0 else 0), dev)
+    if doc_starts is None and not conv_forward and W_init is None and x0_halo is None and W_states is None and \
+            update_mask is None:
         _check(lib().ttt_chunk_apply_update(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
                                             _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
                                             _ptr(conv_w), _ptr(O), _ptr(W_final), _ptr(ws), nbytes, _stream(dev)),
@@ -206,7 +219,8 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
             doc_starts = doc_starts.to(torch.uint8)
         _need(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), torch.uint8, dev)
     ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
-    opts = LayerOptions(ptr(doc_starts), 1 if conv_forward else 0, ptr(W_init), ptr(x0_halo), ptr(W_states))
+    opts = LayerOptions(ptr(doc_starts), 1 if conv_forward else 0, ptr(W_init), ptr(x0_halo), ptr(W_states),
+                        ptr(update_mask))
     _check(lib().ttt_chunk_apply_update_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
                                            _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
                                            _ptr(conv_w), ctypes.byref(opts), _ptr(O), _ptr(W_final), _ptr(ws),
@@ -216,9 +230,10 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
 
 
 def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", O=None, W_final=None,
-                          workspace=None, W_states=None):
+                          workspace=None, W_states=None, update_mask=None):
     """The chunk loop given Z [B, n, f] and Vhat [B, n, d].  Returns (O, W_final).  W_states [B, n // chunk, d, f]
-    (dtype), if given, receives the per-chunk states of the dot objective (ttt_core_apply_update_ex)."""
+    (dtype), if given, receives the per-chunk states of the dot objective; update_mask [B, n // chunk] as for the
+    layer (both through ttt_core_apply_update_ex)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
     dt, dev = Z.dtype, Z.device
@@ -232,9 +247,12 @@ def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", 
     _need(W_final, "W_final", (B, d, f), torch.float32, dev)
     nbytes = ttt_inplace_workspace_bytes(shape, dt, mode, False)
     ws = _workspace(nbytes, dev, workspace)
-    if W_states is not None:
-        _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
-        opts = LayerOptions(None, 0, None, None, ctypes.c_void_p(W_states.data_ptr()) if W_states.numel() else None)
+    update_mask = _flags(update_mask, "update_mask", (B, n // chunk if chunk > 0 else 0), dev)
+    if W_states is not None or update_mask is not None:
+        if W_states is not None:
+            _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
+        ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
+        opts = LayerOptions(None, 0, None, None, ptr(W_states), ptr(update_mask))
         _check(lib().ttt_core_apply_update_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(Z),
                                               _ptr(Vhat), _ptr(W_down0), ctypes.byref(opts), _ptr(O), _ptr(W_final),
                                               _ptr(ws), nbytes, _stream(dev)),

@@ -23,6 +23,7 @@ inline bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
 inline int64_t kstep(int dtype) { return dtype == TTT_BF16 ? 64 : 32; }
 
 struct Plan {
+  int mode;
   int64_t B, n, d, f, C, K, k;
   size_t esz;
   bool fused;
@@ -34,6 +35,7 @@ struct Plan {
   const float* Winit;   // resumed rows: state before chunk 0 [B, d, f] fp32 (device) or null
   const void* halo;     // resumed rows: X0 rows before the first token [B, K-1, d] (device) or null
   void* states;         // dot objective: where the per-chunk states go [B, k, d, f] (device), or null: workspace
+  const uint8_t* umask; // update mask [B, k] (device) or null: every chunk updates
 };
 
 int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
@@ -64,6 +66,8 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   p->Winit = nullptr;
   p->halo = nullptr;
   p->states = nullptr;
+  p->umask = nullptr;
+  p->mode = mode;
   p->B = s->batch;
   p->n = s->seq_len;
   p->d = s->d_model;
@@ -152,7 +156,7 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
     }
     for (int c = 0; c < k; ++c) {
       int st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, p.docs, p.Winit != nullptr, B, n, d, f,
-                                            C, c, eta, s));
+                                            C, c, eta, s, p.umask));
       if (st != TTT_OK) return st;
     }
     return TTT_OK;
@@ -184,7 +188,9 @@ int run_producers(const Plan& p, const void* H, const void* X0, const void* Wg, 
   if (st == TTT_OK) st = dev(ttt::launch_conv<T>((const T*)X0, (const T*)cw, Y, rows, n, d, (int)p.K, p.docs, (int)p.C,
                                                   p.conv_fwd, (const T*)p.halo, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Wt, WtT, 1, d, d, 1.0f, 0, s));
-  if (st == TTT_OK) st = dev(ttt::launch_produce_vhat<T>(Y, WtT, Vt, rows, n, d, vscale, s));
+  // the dot plans zero the targets of chunks that do not update; MSE zeroes their residuals instead
+  const uint8_t* um = p.mode == TTT_MODE_MSE ? nullptr : p.umask;
+  if (st == TTT_OK) st = dev(ttt::launch_produce_vhat<T>(Y, WtT, Vt, rows, n, d, vscale, s, um, (int)p.C));
   return st;
 }
 
@@ -200,6 +206,7 @@ int apply_options(Plan& p, int mode, const ttt_layer_options* o, bool producers)
   p.docs = o->doc_starts;
   p.Winit = o->W_init;
   p.states = o->W_states;
+  p.umask = o->update_mask;
   if (producers) {
     p.conv_fwd = o->conv_forward == 1;
     p.halo = p.K > 1 ? o->x0_halo : nullptr;
@@ -233,7 +240,7 @@ int core(const Plan& p, int mode, float eta, const void* Z, const void* V, const
   int st = dev(ttt::launch_transpose<T>((const T*)Z, Zt, (int)p.B, (int)p.n, (int)p.f, 1.0f, 0, s));
   if (st == TTT_OK)
     st = dev(ttt::launch_transpose<T>((const T*)V, Vt, (int)p.B, (int)p.n, (int)p.d, target_scale(p, mode, eta), 0,
-                                      s));
+                                      s, mode == TTT_MODE_MSE ? nullptr : p.umask, (int)p.C));
   if (st != TTT_OK) return st;
   return run_core<T>(p, mode, eta, Zt, Vt, W0, O, Wf, ws, s);
 }

@@ -25,6 +25,14 @@ __device__ __forceinline__ bool doc_start(const uint8_t* __restrict__ docs, int6
   return docs != nullptr && docs[b * k + c] != 0;
 }
 
+// Update mask [B, k] (device; null: every chunk updates).  A chunk whose flag
+// is zero is applied but leaves the state as it found it; its target (dot
+// objective) or residual (MSE) is multiplied by zero instead, so the update's
+// accumulation adds exact zeros.
+__device__ __forceinline__ float update_flag(const uint8_t* __restrict__ umask, int64_t b, int k, int c) {
+  return umask == nullptr || umask[b * k + c] != 0 ? 1.0f : 0.0f;
+}
+
 
 template <typename T> constexpr int esz() { return (int)sizeof(T); }
 
@@ -211,9 +219,12 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ X0, cons
 // dst[b][c][r] = scale * src[b][r][c] for an R x C matrix per batch entry (64 x 64 tiles).
 // rev > 0: the rows come in blocks of rev (chunks) whose order is reversed in
 // dst, i.e. r lands at column (R / rev - 1 - r / rev) rev + r % rev.
+// umask (with chunk > 0): the rows are tokens of chunks of `chunk` rows, and
+// rows of chunks whose update flag is zero are scaled by zero.
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, T* __restrict__ dst, int R, int C,
-                                                   float scale, int rev) {
+                                                   float scale, int rev, const uint8_t* __restrict__ umask,
+                                                   int chunk) {
   __shared__ T tile[64][65];
   const int64_t b = blockIdx.y;
   const int tc = (C + 63) / 64;
@@ -229,7 +240,8 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, T*
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
     const int rr = rev > 0 ? (R / rev - 1 - r / rev) * rev + r % rev : r;
-    if (c < C && r < R) o[(int64_t)c * R + rr] = scale == 1.0f ? tile[tx][i] : from_f32<T>(scale * to_f32(tile[tx][i]));
+    const float sc = umask != nullptr && r < R ? scale * update_flag(umask, blockIdx.y, R / chunk, r / chunk) : scale;
+    if (c < C && r < R) o[(int64_t)c * R + rr] = sc == 1.0f ? tile[tx][i] : from_f32<T>(sc * to_f32(tile[tx][i]));
   }
 }
 
@@ -406,7 +418,8 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z_bwd(const T* __restrict__ H, const T* __r
 // Q = output channels; writes Vt[b, o, t..t+3].
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_produce_vhat(const T* __restrict__ Y, const T* __restrict__ WtT, T* __restrict__ Vt,
-                                          int64_t rows, int n, int d, float scale) {
+                                          int64_t rows, int n, int d, float scale, const uint8_t* __restrict__ umask,
+                                          int C_) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (int)((rows + G::BP - 1) / G::BP), TQ = (d + G::BQ - 1) / G::BQ;
@@ -428,8 +441,16 @@ TTT_GEMM_KERNEL(Wide) void k_produce_vhat(const T* __restrict__ Y, const T* __re
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
 
   // Vt [b, o, t]: staged as [output channel][token] in as many passes as the
-  // stage area needs (one for bf16, two for fp32).
+  // stage area needs (one for bf16, two for fp32).  A lane's four tokens lie in
+  // one chunk of one batch row (n and C_ are multiples of 8), so they share
+  // one update flag.
   const int tn = (int)min<int64_t>(G::BP, rows - t0);
+  float sc[G::NPB];
+#pragma unroll
+  for (int i = 0; i < G::NPB; ++i) {
+    const int64_t tok = min<int64_t>(t0 + G::acc_p(i, 0), rows - 1), b = tok / n;
+    sc[i] = umask != nullptr ? scale * update_flag(umask, b, n / C_, (int)(tok - b * n) / C_) : scale;
+  }
   constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
   const Staged<T, G::BP> st{smem};
 #pragma unroll
@@ -440,8 +461,8 @@ TTT_GEMM_KERNEL(Wide) void k_produce_vhat(const T* __restrict__ Y, const T* __re
       if (q < 0 || q >= RPP) continue;
 #pragma unroll
       for (int i = 0; i < G::NPB; ++i)
-        st.put4(q, G::acc_p(i, 0), scale * acc[i][j][0], scale * acc[i][j][1], scale * acc[i][j][2],
-                scale * acc[i][j][3]);
+        st.put4(q, G::acc_p(i, 0), sc[i] * acc[i][j][0], sc[i] * acc[i][j][1], sc[i] * acc[i][j][2],
+                sc[i] * acc[i][j][3]);
     }
     __syncthreads();
     st.template flush<G::NT>(RPP, [&](int r, int col) -> T* {
@@ -931,7 +952,7 @@ template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __restrict__ W0,
                                        const T* __restrict__ Wcur, T* __restrict__ O, const T* __restrict__ Vt,
                                        T* __restrict__ Rt, const uint8_t* __restrict__ docs, int n, int d, int f,
-                                       int C_, int c, float rscale, bool cont) {
+                                       int C_, int c, float rscale, bool cont, const uint8_t* __restrict__ umask) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
@@ -943,6 +964,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
   const int i0 = tp * G::BP, t0 = tq * G::BQ;
   const int64_t row0 = (int64_t)b * n + (int64_t)c * C_ + t0;
   const uint64_t ldb = (uint64_t)f * esz<T>();
+  rscale *= update_flag(umask, b, n / C_, c);       // a masked chunk's update adds zeros
 
   DmaOp<G::NW, G::BP> op;
   DmaOpMN<T, G::NW, G::BQ> oq;
@@ -1119,10 +1141,11 @@ hipError_t launch_produce_z_bwd(const T* H, const T* Wg, const T* Wu, const T* d
 }
 
 template <typename T>
-hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int Cs, float scale, int rev, hipStream_t s) {
+hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int Cs, float scale, int rev, hipStream_t s,
+                            const uint8_t* umask, int chunk) {
   if (batch == 0 || R == 0 || Cs == 0) return hipSuccess;
-  k_transpose<T><<<dim3((unsigned)(cdiv(Cs, 64) * cdiv(R, 64)), (unsigned)batch), 256, 0, s>>>(src, dst, R, Cs, scale,
-                                                                                             rev);
+  k_transpose<T><<<dim3((unsigned)(cdiv(Cs, 64) * cdiv(R, 64)), (unsigned)batch), 256, 0, s>>>(
+      src, dst, R, Cs, scale, rev, chunk > 0 ? umask : nullptr, chunk);
   return hipGetLastError();
 }
 
@@ -1136,9 +1159,10 @@ hipError_t launch_produce_z(const T* H, const T* Wg, const T* Wu, T* Z, T* Zt, i
 
 template <typename T>
 hipError_t launch_produce_vhat(const T* Y, const T* WtT, T* Vt, int64_t rows, int n, int d, float scale,
-                               hipStream_t s) {
+                               hipStream_t s, const uint8_t* umask, int C) {
   if (rows == 0) return hipSuccess;
-  k_produce_vhat<T><<<tiles_u(cdiv(rows, kWB) * cdiv(d, kWB)), Wide::NT, 0, s>>>(Y, WtT, Vt, rows, n, d, scale);
+  k_produce_vhat<T><<<tiles_u(cdiv(rows, kWB) * cdiv(d, kWB)), Wide::NT, 0, s>>>(Y, WtT, Vt, rows, n, d, scale,
+                                                                                  C > 0 ? umask : nullptr, C);
   return hipGetLastError();
 }
 
@@ -1226,9 +1250,9 @@ hipError_t launch_zero(T* p, int64_t n, hipStream_t s) {
 template <typename T>
 hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
                             T* Rt, const uint8_t* docs, bool cont, int B, int n, int d, int f, int Cs, int c,
-                            float eta, hipStream_t s) {
+                            float eta, hipStream_t s, const uint8_t* umask) {
   k_mse_apply<T><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, docs, n, d,
-                                                                              f, Cs, c, -eta / (float)Cs, cont);
+                                                                              f, Cs, c, -eta / (float)Cs, cont, umask);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, docs, n, d, f,
@@ -1259,10 +1283,12 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
 #define TTT_INST(T)                                                                                               \
   template hipError_t launch_conv<T>(const T*, const T*, T*, int64_t, int, int, int, const uint8_t*, int, bool,  \
                                      const T*, hipStream_t);                                                      \
-  template hipError_t launch_transpose<T>(const T*, T*, int, int, int, float, int, hipStream_t);                 \
+  template hipError_t launch_transpose<T>(const T*, T*, int, int, int, float, int, hipStream_t, const uint8_t*,   \
+                                          int);                                                                   \
   template hipError_t launch_produce_z<T>(const T*, const T*, const T*, T*, T*, int64_t, int, int, int,          \
                                           hipStream_t);                                                           \
-  template hipError_t launch_produce_vhat<T>(const T*, const T*, T*, int64_t, int, int, float, hipStream_t);     \
+  template hipError_t launch_produce_vhat<T>(const T*, const T*, T*, int64_t, int, int, float, hipStream_t,      \
+                                             const uint8_t*, int);                                                \
   template hipError_t launch_chunk_delta<T>(const T*, const T*, float*, int, int, int, int, int, hipStream_t);   \
   template hipError_t launch_chunk_scan<T>(const float*, const T*, T*, float*, int, int, int64_t, float,         \
                                            const uint8_t*, const float*, hipStream_t);                            \
@@ -1280,7 +1306,8 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
                                          hipStream_t);                                                            \
   template hipError_t launch_zero<T>(T*, int64_t, hipStream_t);                                                   \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
-                                          const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t); \
+                                          const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t,  \
+                                          const uint8_t*);                                                        \
   template hipError_t launch_state_copy<T>(const float*, float*, T*, int, int64_t, hipStream_t);
 TTT_INST(float)
 TTT_INST(bf16)

@@ -12,13 +12,16 @@ template <typename T>
 hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int d, int K, const uint8_t* docs, int C,
                        bool fwd, const T* halo, hipStream_t s);
 template <typename T>
-hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int C, float scale, int rev, hipStream_t s);
+// umask (with chunk > 0): rows of chunks whose update flag [batch, R / chunk]
+// is zero are scaled by zero.
+hipError_t launch_transpose(const T* src, T* dst, int batch, int R, int C, float scale, int rev, hipStream_t s,
+                            const uint8_t* umask = nullptr, int chunk = 0);
 template <typename T>
 hipError_t launch_produce_z(const T* H, const T* Wg, const T* Wu, T* Z, T* Zt, int64_t rows, int n, int d, int f,
                             hipStream_t s);
 template <typename T>
 hipError_t launch_produce_vhat(const T* Y, const T* WtT, T* Vt, int64_t rows, int n, int d, float scale,
-                               hipStream_t s);
+                               hipStream_t s, const uint8_t* umask = nullptr, int C = 0);
 template <typename T>
 hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n, int d, int f, int C, hipStream_t s);
 template <typename T>
@@ -94,7 +97,7 @@ hipError_t launch_zero(T* p, int64_t n, hipStream_t s);
 template <typename T>
 hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
                             T* Rt, const uint8_t* docs, bool cont, int B, int n, int d, int f, int C, int c,
-                            float eta, hipStream_t s);
+                            float eta, hipStream_t s, const uint8_t* umask = nullptr);
 template <typename T>
 hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64_t df, hipStream_t s);
 

@@ -167,6 +167,14 @@ typedef struct {
    * them costs nothing.  ttt_core_backward takes them to skip recomputing
    * the states.  NULL: not kept.  With the MSE objective: TTT_ERR_ARG. */
   void* W_states;
+  /* Strided updates (the block-wise mask of the LaCT review's section on the
+   * order of the apply and update operations, read onto this layer):
+   * [B, k] uint8, DEVICE; a zero entry means chunk c of that row is applied
+   * but does not update the state (its update adds exact zeros: the dot
+   * objective's target, or the MSE residual, is multiplied by zero), so the
+   * next chunk sees the same state.  A document start still resets to
+   * W_down0.  NULL: every chunk updates. */
+  const unsigned char* update_mask;
 } ttt_layer_options;
 
 /* The layer of ttt_chunk_apply_update with options (above); same arguments,
@@ -185,9 +193,9 @@ int ttt_core_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, f
                           void* O, float* W_final, void* workspace, size_t workspace_bytes,
                           void* stream);
 
-/* The chunk loop with options: doc_starts, W_init and W_states as for the
- * layer (conv_forward and x0_halo concern the target producer and are not
- * read). */
+/* The chunk loop with options: doc_starts, W_init, W_states and update_mask
+ * as for the layer (conv_forward and x0_halo concern the target producer and
+ * are not read). */
 int ttt_core_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mode, float eta,
                              const void* Z, const void* Vhat, const void* W_down0,
                              const ttt_layer_options* options, void* O, float* W_final,

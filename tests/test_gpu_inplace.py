@@ -223,6 +223,68 @@ def test_layer_chunk_synchronous_tile_order(mode):
     check_layer(cfg, x, O, Wf)
 
 
+LAYER_W = ("H", "X0", "W_gate", "W_up", "W_down0", "W_target", "conv_w")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["dot", "dot_scan", "mse"])
+def test_layer_update_mask(dtype, mode):
+    """Strided updates (update_mask): flagged chunks update, the others are applied with the state they find,
+    against the oracle with the same mask.  Row 0 updates on every other chunk (the first one masked), row 1 on
+    none but the last, row 2 masks two chunks and also starts a document at chunk 3, row 3 updates everywhere.
+    An all-ones mask gives the unmasked call's bits."""
+    eta = 0.05 if mode != "mse" else 0.5
+    cfg = small_cfg(dtype, mode, B=4, n=1536, d=264, f=392, C=256, eta=eta)
+    k = cfg.seq_len // cfg.chunk
+    mask = np.ones((4, k), dtype=np.uint8)
+    mask[0, 0::2] = 0
+    mask[1, :-1] = 0
+    mask[2, [1, 4]] = 0
+    starts = np.zeros((4, k), dtype=np.uint8)
+    starts[2, 3] = 1
+    x = ti.inplace_inputs(cfg)
+    g = dev(x)
+    args = tuple(g[n] for n in LAYER_W)
+    O, Wf = cw.ttt_chunk_apply_update(*args, cfg.chunk, cfg.eta, mode, update_mask=torch.from_numpy(mask).cuda(),
+                                      doc_starts=torch.from_numpy(starts).cuda())
+    O1, W1 = cw.ttt_chunk_apply_update(*args, cfg.chunk, cfg.eta, mode,
+                                       update_mask=torch.ones(4, k, dtype=torch.uint8, device="cuda"))
+    O0, W0g = cw.ttt_chunk_apply_update(*args, cfg.chunk, cfg.eta, mode)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O0) and torch.equal(W1, W0g)
+    Oref, Wref = orc.inplace_layer(*(ti.to_f64(x[n]) for n in LAYER_W), cfg.chunk, cfg.eta,
+                                   "dot" if mode == "dot_scan" else mode, update_mask=mask, doc_starts=starts)
+    W0 = ti.to_f64(x["W_down0"])
+    for b in range(4):
+        assert rel(f64(O[b]), Oref[b]) < TOL[dtype], b
+        assert rel(f64(Wf[b]), Wref[b]) < TOL[dtype] and rel(f64(Wf[b]) - W0, Wref[b] - W0) < TOL[dtype], b
+    # row 1 updates only on its last chunk: every earlier chunk is applied with W_down0
+    Z1 = orc.gated_intermediate(ti.to_f64(x["H"])[1, : (k - 1) * cfg.chunk], ti.to_f64(x["W_gate"]),
+                                ti.to_f64(x["W_up"]))
+    assert rel(f64(O[1, : (k - 1) * cfg.chunk]), Z1 @ W0.T) < TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_core_update_mask_is_a_zero_target(dtype):
+    """The chunk loop given Z and V^ (dot objective): masking a chunk is, bit for bit, zeroing its targets."""
+    cfg = small_cfg(dtype, "dot", B=2, n=1024, C=256)
+    gz = torch.Generator().manual_seed(3)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Z = (torch.randn(2, 1024, 392, generator=gz) * 0.6).to(tdt).cuda()
+    V = torch.randn(2, 1024, 264, generator=gz).to(tdt).cuda()
+    W0 = (torch.randn(264, 392, generator=gz) * 0.05).to(tdt).cuda()
+    mask = torch.tensor([[1, 0, 0, 1], [0, 1, 1, 1]], dtype=torch.uint8)
+    Vz = V.clone()
+    for b in range(2):
+        for c in range(4):
+            if not mask[b, c]:
+                Vz[b, c * 256:(c + 1) * 256] = 0
+    O, Wf = cw.ttt_core_apply_update(Z, V, W0, 256, 0.05, "dot", update_mask=mask.cuda())
+    Oz, Wz = cw.ttt_core_apply_update(Z, Vz, W0, 256, 0.05, "dot")
+    torch.cuda.synchronize()
+    assert torch.equal(O, Oz) and torch.equal(Wf, Wz)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["dot", "dot_scan", "mse"])
 def test_layer_packed_documents(dtype, mode):
