@@ -69,6 +69,9 @@ struct TileCfg {
   __device__ static __forceinline__ int acc_q(int j) { return (wave_id() % WQ) * (BM * NQB) + j * BM + (lane_id() & 15); }
 };
 using Wide = TileCfg<2, 4, 8, 4>;
+// 128 x 128 tiles of 4 waves and 64 KB of LDS, two workgroups per CU: for
+// launches with too few 256 x 256 tiles to fill the GPU.
+using Half = TileCfg<2, 2, 4, 4>;
 
 // Kernel attributes: NT threads, and the number of waves per SIMD the register
 // budget is planned for (the scheduler then spends registers on keeping LDS

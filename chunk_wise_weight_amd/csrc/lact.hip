@@ -516,10 +516,13 @@ __global__ __launch_bounds__(256) void k_muon_prep(const float* __restrict__ par
 //   STEP 2: Xn = a X + B X             P = X columns (MN),    Q = B rows,  K = r
 // Output row-major, rows indexed by Q and columns by P, so that a lane's four
 // accumulators are four consecutive elements of one row.
+// The matrices are small (a few hundred 256 x 256 tiles at most over all of a
+// step's gradients), so the GEMMs take the 128 x 128 tile of 4 waves, two
+// workgroups per CU (register budget of two waves per SIMD).
 template <typename T, int STEP>
-TTT_GEMM_KERNEL(Wide) void k_ns_gemm(const T* __restrict__ X, const T* __restrict__ A, const T* __restrict__ Bm,
-                                     T* __restrict__ out, int r, int c) {
-  using G = Wide;
+__global__ __launch_bounds__(Half::NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_ns_gemm(
+    const T* __restrict__ X, const T* __restrict__ A, const T* __restrict__ Bm, T* __restrict__ out, int r, int c) {
+  using G = Half;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int mat = blockIdx.y;
   const int cols = STEP == 2 ? c : r, rows = r;
@@ -766,8 +769,8 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
     if (want()) k_lact_grad<T><<<(unsigned)tg, Wide::NT, 0, s>>>(kk, dA, dU, Hh, R, part, BH, n, dh, m, C, sr.kc, sr.nk, kslice);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.muon) {
-      const dim3 nsr((unsigned)(cdiv(mr, Wide::BP) * cdiv(mr, Wide::BQ)), (unsigned)(3 * BH));
-      const dim3 nsx((unsigned)(cdiv(mc, Wide::BP) * cdiv(mr, Wide::BQ)), (unsigned)(3 * BH));
+      const dim3 nsr((unsigned)(cdiv(mr, Half::BP) * cdiv(mr, Half::BQ)), (unsigned)(3 * BH));
+      const dim3 nsx((unsigned)(cdiv(mc, Half::BP) * cdiv(mr, Half::BQ)), (unsigned)(3 * BH));
       if (want()) k_muon_norm<<<dim3(kMuonNormBlocks, (unsigned)(3 * BH)), 256, 0, s>>>(part, mnorm, BH, md);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if (want())
@@ -776,11 +779,11 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
       T* xs = mX0;
       T* xn = mX1;
       for (int it = 0; it < kMuonSteps; ++it) {
-        if (want()) k_ns_gemm<T, 0><<<nsr, Wide::NT, 0, s>>>(xs, nullptr, nullptr, mA, mr, mc);
+        if (want()) k_ns_gemm<T, 0><<<nsr, Half::NT, 0, s>>>(xs, nullptr, nullptr, mA, mr, mc);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (want()) k_ns_gemm<T, 1><<<nsr, Wide::NT, 0, s>>>(nullptr, mA, nullptr, mB, mr, mc);
+        if (want()) k_ns_gemm<T, 1><<<nsr, Half::NT, 0, s>>>(nullptr, mA, nullptr, mB, mr, mc);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if (want()) k_ns_gemm<T, 2><<<nsx, Wide::NT, 0, s>>>(xs, nullptr, mB, xn, mr, mc);
+        if (want()) k_ns_gemm<T, 2><<<nsx, Half::NT, 0, s>>>(xs, nullptr, mB, xn, mr, mc);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         T* t = xs;
         xs = xn;
