@@ -171,7 +171,7 @@ def chunk_apply_update(Z, Vhat, W0, chunk, eta, mode):
     return O, W
 
 
-def chunk_core_backward(Z, Vhat, W0, chunk, eta, dO):
+def chunk_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None):
     """Gradients of a loss through the dot-objective chunk loop (chunk_apply_update
     with mode "dot"), given dO = dLoss/dO: returns (dZ [n, f], dVhat [n, d],
     dW0 [d, f]).  The chain rule through O_c = Z_c W_c^T (eq. (3)) and
@@ -181,25 +181,36 @@ def chunk_core_backward(Z, Vhat, W0, chunk, eta, dO):
       dZ_j    = dO_j W_j + eta Vhat_j S_j,
       dVhat_j = eta Z_j S_j^T,
       dW0     = sum_c dW_c.
+    `doc_starts` [n_chunks] (truthy entries; chunk 0 always starts one) packs
+    documents as in inplace_layer: the state restarts from W0 at each start, so
+    a delta reaches only the later states of its own document, the suffix
+    sums run to the end of the document, and W0 receives every document's sum.
     The loss is taken to depend on O only (not on W_final)."""
     Z, Vhat, W0, dO = _f64(Z), _f64(Vhat), _f64(W0), _f64(dO)
     n = Z.shape[0]
     bounds = [(s, min(s + chunk, n)) for s in range(0, n, chunk)]
+    starts = [c == 0 or (doc_starts is not None and bool(doc_starts[c])) for c in range(len(bounds))]
     states = []                                   # W_c, the state chunk c is applied with
     W = W0.copy()
-    for (s, e) in bounds:
+    for c, (s, e) in enumerate(bounds):
+        if starts[c]:
+            W = W0.copy()
         states.append(W)
         W = W + eta * (Vhat[s:e].T @ Z[s:e])
     dWc = [dO[s:e].T @ Z[s:e] for (s, e) in bounds]
     dZ = np.empty_like(Z)
     dV = np.empty_like(Vhat)
-    S = np.zeros_like(W0)                         # sum of dW_c over the chunks after the current one
+    dW0 = np.zeros_like(W0)
+    S = np.zeros_like(W0)                         # sum of dW_c over the later chunks of the current document
     for c in range(len(bounds) - 1, -1, -1):
         s, e = bounds[c]
         dZ[s:e] = dO[s:e] @ states[c] + eta * (Vhat[s:e] @ S)
         dV[s:e] = eta * (Z[s:e] @ S.T)
         S = S + dWc[c]
-    return dZ, dV, S
+        if starts[c]:                             # the document's first chunk: its sum reaches W0
+            dW0 = dW0 + S
+            S = np.zeros_like(W0)
+    return dZ, dV, dW0
 
 
 def chunk_prefix_form(Z, Vhat, W0, chunk, eta):

@@ -673,3 +673,28 @@ def test_update_mask_mse_equals_resumed_calls_with_a_frozen_chunk():
                                x0_halo=halo(2))
     np.testing.assert_allclose(O, np.concatenate([Oa, Ob, Oc], axis=1), rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(W, Wc, rtol=1e-12, atol=1e-12)
+
+
+def test_core_backward_with_documents_matches_autograd():
+    """Packed documents: autograd of the chunk loop that restarts from W0 at every flagged chunk."""
+    rng = _rng(54)
+    n, C, d, f, eta = 15, 3, 3, 4, 0.3
+    starts = np.array([1, 0, 1, 1, 0])
+    Z, V, W0, dO = (rng.standard_normal(s) for s in ((n, f), (n, d), (d, f), (n, d)))
+    dZ, dV, dW0 = orc.chunk_core_backward(Z, V, W0, C, eta, dO, doc_starts=starts)
+    tz, tv, tw = (torch.tensor(a, requires_grad=True) for a in (Z, V, W0))
+    W, outs = tw, []
+    for c, s in enumerate(range(0, n, C)):
+        if starts[c]:
+            W = tw
+        outs.append(tz[s:s + C] @ W.T)
+        W = W + eta * (tv[s:s + C].T @ tz[s:s + C])
+    (torch.cat(outs) * torch.from_numpy(dO)).sum().backward()
+    np.testing.assert_allclose(dZ, tz.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dV, tv.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dW0, tw.grad.numpy(), rtol=1e-12, atol=1e-12)
+    # and the forward it differentiates is the layer's packed-document chunk loop
+    O_loop = torch.cat(outs).detach().numpy()
+    O_docs = np.concatenate([orc.chunk_apply_update(Z[a:b], V[a:b], W0, C, eta, "dot")[0]
+                             for a, b in ((0, 6), (6, 9), (9, 15))])
+    np.testing.assert_allclose(O_loop, O_docs, rtol=1e-12, atol=1e-12)
