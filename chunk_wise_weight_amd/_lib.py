@@ -63,7 +63,8 @@ _SIGNATURES = {
     "ttt_core_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
     "ttt_layer_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
     "ttt_layer_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 17 + [_S, _P]),
-    "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+                               _P]),
     "ttt_produce_z": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P, _P]),
     "ttt_vhat_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, ctypes.POINTER(_S)]),
     "ttt_produce_vhat": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _S, _P]),
@@ -273,10 +274,10 @@ def ttt_core_backward_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, s
 
 
 def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVhat=None, dW_down0=None,
-                      workspace=None, W_states=None):
+                      workspace=None, W_states=None, doc_starts=None):
     """Gradients through the dot chunk loop given dO = dLoss/dO [B, n, d], with the per-chunk states W_states
-    [B, n // chunk, d, f] kept by the forward call, or recomputed (None).
-    Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
+    [B, n // chunk, d, f] kept by the forward call, or recomputed (None); doc_starts [B, n // chunk] packs documents
+    as for the forward layer.  Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
     dt, dev = Z.dtype, Z.device
@@ -296,8 +297,10 @@ def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVh
     nbytes = ttt_core_backward_workspace_bytes(shape, dt, W_states is not None)
     ws = _workspace(nbytes, dev, workspace)
     sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
+    doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
+    dp = ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None and doc_starts.numel() else None
     _check(lib().ttt_core_backward(ctypes.byref(shape), _dt(dt), float(eta), _ptr(Z), _ptr(Vhat), _ptr(W_down0),
-                                   _ptr(dO), sp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
+                                   _ptr(dO), sp, dp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
                                    _stream(dev)),
            "ttt_core_backward")
     return dZ, dVhat, dW_down0

@@ -259,11 +259,13 @@ struct BwdPlan {
   size_t esz;
   bool fused;
   bool saved;         // the states come from the caller
+  const uint8_t* docs;  // document starts [B, k] (device) or null
   int S;
-  size_t off_Zt, off_Vt, off_Vs, off_Zr, off_Gr, off_Wc, off_Sr, off_T, off_zero, off_Wp, off_Tot, off_dW, total;
+  size_t off_Zt, off_Vt, off_Vs, off_Zr, off_Gr, off_Wc, off_Sr, off_T, off_zero, off_Wp, off_Tot, off_dW, off_rd,
+      total;
 };
 
-int make_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, BwdPlan* p) {
+int make_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, BwdPlan* p, bool docs = false) {
   int st = check_inplace_shape(s, dtype);
   if (st != TTT_OK) return st;
   memset(p, 0, sizeof(*p));
@@ -301,6 +303,7 @@ int make_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, BwdPlan* p)
   } else if (!p->fused) {
     take(&p->off_dW, BK * DF * 4);
   }
+  if (docs) take(&p->off_rd, BK);
   p->total = off;
   return TTT_OK;
 }
@@ -311,15 +314,15 @@ int make_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, BwdPlan* p)
 // token-contiguous copies (in the order wanted) and a scan with eta.
 template <typename T>
 int bwd_scan(const BwdPlan& p, const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, float eta, bool rev,
-             char* ws, hipStream_t s) {
+             char* ws, hipStream_t s, const uint8_t* docs = nullptr) {
   const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
   if (p.fused)
     return dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (T*)(ws + p.off_Wp), (float*)(ws + p.off_Tot), B,
-                                                n, d, f, C, p.S, nullptr, nullptr, s,
+                                                n, d, f, C, p.S, docs, nullptr, s,
                                                 rev ? ttt::kScanRowMajorReversed : ttt::kScanRowMajor));
   float* dW = (float*)(ws + p.off_dW);
   int st = dev(ttt::launch_chunk_delta<T>(Zt, Vt, dW, B, n, d, f, C, s));
-  if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, (int64_t)d * f, eta, nullptr, nullptr, s));
+  if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, (int64_t)d * f, eta, docs, nullptr, s));
   return st;
 }
 
@@ -343,11 +346,19 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
   const T* Slast = Sr + (int64_t)(k - 1) * df;      // S_c = Sr[k - 1 - c]: stride -df from here
   int st = dev(ttt::launch_zero<T>(Z0, df, s));
   if (st == TTT_OK && !vs_ready) st = dev(ttt::launch_scale<T>(V, Vs, (int64_t)B * n * d, eta, s));
+  // with packed documents the suffixes restart at each document's end (the reversed order's starts), and
+  // dW_down0, every document's sum, comes from a contraction over all chunks (into Sr and Tt, before the suffixes)
+  const uint8_t* rd = p.docs != nullptr ? (const uint8_t*)(ws + p.off_rd) : nullptr;
+  if (st == TTT_OK && rd != nullptr) st = dev(ttt::launch_rev_docs(p.docs, (uint8_t*)rd, B, k, s));
   if (p.fused) {
-    // W_c (its W_final lands in Tt and is overwritten by the second scan)
-    if (st == TTT_OK && !p.saved) st = bwd_scan<T>(p, Z, Vs, (const T*)W0, Wc, Tt, eta, false, ws, s);
-    // last chunk first: Sr[t] = sum of dO_c^T Z_c over the chunks c > k - 1 - t; Tt = all chunks
-    if (st == TTT_OK) st = bwd_scan<T>(p, Z, dO, Z0, Sr, Tt, 1.0f, true, ws, s);
+    // W_c (its W_final lands in Tt and is overwritten by the scans after it)
+    if (st == TTT_OK && !p.saved) st = bwd_scan<T>(p, Z, Vs, (const T*)W0, Wc, Tt, eta, false, ws, s, p.docs);
+    if (st == TTT_OK && rd != nullptr) {
+      st = bwd_scan<T>(p, Z, dO, Z0, Sr, Tt, 1.0f, false, ws, s);
+      if (st == TTT_OK) st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
+    }
+    // last chunk first: Sr[t] = sum of dO_c^T Z_c over the chunks c > k - 1 - t (of the same document); Tt = all
+    if (st == TTT_OK) st = bwd_scan<T>(p, Z, dO, Z0, Sr, Tt, 1.0f, true, ws, s, rd);
     if (st == TTT_OK)
       st = dev(ttt::launch_apply<T>(Z, Slast, (int64_t)k * df, -df, (T*)dV, B, n, d, f, C, eta, s, true));
   } else {
@@ -359,15 +370,19 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
     if (st == TTT_OK && !p.saved) st = dev(ttt::launch_transpose<T>(V, Vt, B, n, d, 1.0f, 0, s));
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zr, B, n, f, 1.0f, C, s));
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(dO, Gr, B, n, d, 1.0f, C, s));
-    if (st == TTT_OK && !p.saved) st = bwd_scan<T>(p, Zt, Vt, (const T*)W0, Wc, Tt, eta, false, ws, s);
-    if (st == TTT_OK) st = bwd_scan<T>(p, Zr, Gr, Z0, Sr, Tt, 1.0f, true, ws, s);
+    if (st == TTT_OK && !p.saved) st = bwd_scan<T>(p, Zt, Vt, (const T*)W0, Wc, Tt, eta, false, ws, s, p.docs);
+    if (st == TTT_OK && rd != nullptr) {
+      st = bwd_scan<T>(p, Zr, Gr, Z0, Sr, Tt, 1.0f, true, ws, s);
+      if (st == TTT_OK) st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
+    }
+    if (st == TTT_OK) st = bwd_scan<T>(p, Zr, Gr, Z0, Sr, Tt, 1.0f, true, ws, s, rd);
     if (st == TTT_OK)
       st = dev(ttt::launch_apply<T>(Zt, Slast, (int64_t)k * df, -df, (T*)dV, B, n, d, f, C, eta, s));
   }
   if (st == TTT_OK)
     st = dev(ttt::launch_dz<T>(dO, Vs, Wc, (int64_t)k * df, df, Slast, (int64_t)k * df, -df, (T*)dZ, B, n, d, f, C,
                                s));
-  if (st == TTT_OK) st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
+  if (st == TTT_OK && rd == nullptr) st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
   return st;
 }
 
@@ -602,18 +617,19 @@ int ttt_core_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mode
 int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states, size_t* bytes) {
   if (bytes == nullptr) return TTT_ERR_ARG;
   BwdPlan p;
-  int st = make_bwd_plan(shape, dtype, saved_states != 0, &p);
+  int st = make_bwd_plan(shape, dtype, saved_states != 0, &p, true);
   if (st != TTT_OK) return st;
   *bytes = p.total;
   return TTT_OK;
 }
 
 int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
-                      const void* W_down0, const void* dO, const void* W_states, void* dZ, void* dVhat,
-                      float* dW_down0, void* workspace, size_t workspace_bytes, void* stream) {
+                      const void* W_down0, const void* dO, const void* W_states, const unsigned char* doc_starts,
+                      void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes, void* stream) {
   BwdPlan p;
-  int st = make_bwd_plan(shape, dtype, W_states != nullptr, &p);
+  int st = make_bwd_plan(shape, dtype, W_states != nullptr, &p, true);
   if (st != TTT_OK) return st;
+  p.docs = doc_starts;
   if (!finite(eta)) return TTT_ERR_ARG;
   if (!ok_ptr(dW_down0) || (W_states != nullptr && !aligned16(W_states))) return TTT_ERR_ARG;
   if (p.B * p.n > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(W_down0) || !ok_ptr(dO) || !ok_ptr(dZ) ||

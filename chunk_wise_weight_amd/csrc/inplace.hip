@@ -923,6 +923,19 @@ __global__ __launch_bounds__(256) void k_sum_rows(const float* __restrict__ Tot,
   store4(out + e, s[0], s[1], s[2], s[3]);
 }
 
+// Document starts of the reversed chunk order, for the suffix scan of the
+// backward: reversed chunk t is chunk k - 1 - t, and it starts a document of
+// the reversed order when chunk k - t starts one (chunk k - 1 - t ends its
+// document); reversed chunk 0 always does.  docs, rd: [B, k].
+__global__ __launch_bounds__(256) void k_rev_docs(const uint8_t* __restrict__ docs, uint8_t* __restrict__ rd, int B,
+                                                  int k) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)B * k) return;
+  const int64_t b = e / k;
+  const int t = (int)(e - b * k);
+  rd[e] = t == 0 ? 1 : (docs[b * k + (k - t)] != 0 ? 1 : 0);
+}
+
 // dst = scale * src over n elements, four per thread (n % 4 == 0).
 template <typename T>
 __global__ __launch_bounds__(256) void k_scale(const T* __restrict__ src, T* __restrict__ dst, int64_t n,
@@ -1215,6 +1228,12 @@ hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O,
     k_apply<T, true><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, W, wsb, wsc, O, n, d, f, Cs, oscale);
   else
     k_apply<T, false><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, W, wsb, wsc, O, n, d, f, Cs, oscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_rev_docs(const uint8_t* docs, uint8_t* rd, int B, int k, hipStream_t s) {
+  if ((int64_t)B * k == 0) return hipSuccess;
+  k_rev_docs<<<(unsigned)cdiv((int64_t)B * k, 256), 256, 0, s>>>(docs, rd, B, k);
   return hipGetLastError();
 }
 

@@ -63,6 +63,8 @@ inline int update_scan_segments(int64_t d, int64_t f, int64_t k, int64_t C) {
 template <typename T>
 hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O, int B, int n, int d, int f, int C,
                         float oscale, hipStream_t s, bool znat = false);
+// rd [B, k]: the document starts of the reversed chunk order (see k_rev_docs).
+hipError_t launch_rev_docs(const uint8_t* docs, uint8_t* rd, int B, int k, hipStream_t s);
 // dst [n] = scale * src (n % 4 == 0).
 template <typename T>
 hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_t s);

@@ -228,14 +228,20 @@ int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype,
  * scan run over the chunks in reverse order on (Z, dO) from a zero state, so
  * each S_c is a sum of its own terms, never a difference of prefix sums.
  * With bf16 the states W_c and S_c are held in bf16 (fp32 accumulation), as in
- * the forward call.  Rows are single documents starting at W_down0 (no
- * document starts, resumed state or update mask).  Inputs as in
+ * the forward call.  doc_starts [B, k] (DEVICE, as ttt_layer_options.
+ * doc_starts; NULL: one document per row) packs documents: the states
+ * restart from W_down0 at each start, each suffix S_c runs to the end of c's
+ * document (the reversed scan restarts from zero where the forward order's
+ * documents end), and dW_down0 receives every document's sum, formed by one
+ * more contraction over all chunks (2 d f flop per token).  Resumed rows and
+ * update masks are not handled.  Inputs as in
  * ttt_core_apply_update; conv_k is not used.  seq_len == 0 or batch == 0
  * gives dW_down0 = 0 and touches nothing else.  Errors as for every entry
  * point (a too small workspace: TTT_ERR_WORKSPACE). */
 int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
-                      const void* W_down0, const void* dO, const void* W_states, void* dZ, void* dVhat,
-                      float* dW_down0, void* workspace, size_t workspace_bytes, void* stream);
+                      const void* W_down0, const void* dO, const void* W_states, const unsigned char* doc_starts,
+                      void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes,
+                      void* stream);
 
 /* ---- backward of the whole dot layer ---- */
 

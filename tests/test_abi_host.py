@@ -210,7 +210,7 @@ def test_backward_workspace_and_validation():
     B, n, d, f, C = 2, 2048, 256, 512, 256      # fused, four segments (as the forward plan of this shape)
     k, e = n // C, 2
     states = al(B * k * d * f * e)
-    base = al(B * n * d * e) + states + al(B * d * f * 4) + al(d * f * e)
+    base = al(B * n * d * e) + states + al(B * d * f * 4) + al(d * f * e) + al(B * k)    # + reversed doc starts
     seg = al(B * (k - k // 4) * d * f * e) + al(B * 3 * d * f * 4)
     assert ws(B, n, d, f, C) == (cw.TTT_OK, base + states + seg)
     assert ws(B, n, d, f, C, saved=1) == (cw.TTT_OK, base + seg)
@@ -219,7 +219,7 @@ def test_backward_workspace_and_validation():
     k2 = n2 // C2
     base2 = al(B * n2 * d * e) + 2 * (al(B * n2 * d * e) + al(B * n2 * f * e)) + 2 * al(B * k2 * d * f * e) + \
         al(B * d * f * 4) + al(d * f * e)
-    assert ws(B, n2, d, f, C2) == (cw.TTT_OK, base2 + al(B * k2 * d * f * 4))
+    assert ws(B, n2, d, f, C2) == (cw.TTT_OK, base2 + al(B * k2 * d * f * 4) + al(B * k2))
     assert ws(0, n, d, f, C) == (cw.TTT_OK, 0) and ws(B, 0, d, f, C) == (cw.TTT_OK, 0)
     assert ws(B, 2000, d, f, C)[0] == cw.TTT_ERR_SHAPE
     assert lib.ttt_core_backward_workspace_bytes(ctypes.byref(cw.InplaceShape(B, n, d, f, C, 1)), cw.TTT_BF16, 0,
@@ -230,7 +230,7 @@ def test_backward_workspace_and_validation():
     outs = [_fake() for _ in range(2)]   # dZ, dVhat
 
     def call(eta, ins, Ws, outs, dW, w, nbytes, dtype=cw.TTT_BF16):
-        return lib.ttt_core_backward(ctypes.byref(s), dtype, eta, *ins, Ws, *outs, dW, w, nbytes, None)
+        return lib.ttt_core_backward(ctypes.byref(s), dtype, eta, *ins, Ws, None, *outs, dW, w, nbytes, None)
 
     assert call(0.1, ins, None, outs, _fake(), _fake(), nb - 1) == cw.TTT_ERR_WORKSPACE
     assert call(0.1, ins, None, outs, _fake(), None, nb) == cw.TTT_ERR_WORKSPACE

@@ -102,6 +102,29 @@ def test_backward_rows_independent():
     assert rel(f64(dW0), oracle(x, cfg)[2]) < TOL["bf16"]
 
 
+# packed documents: row 0 starts one every other chunk, row 1 at every chunk, row 2 holds one document; on the fused
+# scan with two segments (k = 6: a segment starts inside a document, in both scan orders) and on the delta + scan path
+@pytest.mark.parametrize("dtype,C,k", [("bf16", 128, 6), ("f32", 96, 4), ("bf16", 72, 4)])
+def test_backward_packed_documents(dtype, C, k):
+    cfg = cfg_of(dtype, 3, k, C)
+    x = ti.backward_inputs(cfg)
+    g = {name: t.cuda() for name, t in x.items()}
+    starts = np.zeros((3, k), dtype=np.uint8)
+    starts[0, ::2] = 1
+    starts[1, :] = 1
+    dZ, dV, dW0 = cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta,
+                                       doc_starts=torch.from_numpy(starts).cuda())
+    torch.cuda.synchronize()
+    Z, V, W0, dO = (ti.to_f64(x[name]) for name in ("Z", "Vhat", "W_down0", "dO"))
+    outs = [orc.chunk_core_backward(Z[b], V[b], W0, C, cfg.eta, dO[b], doc_starts=starts[b]) for b in range(3)]
+    for b in range(3):
+        assert rel(f64(dZ[b]), outs[b][0]) < TOL[dtype], b
+        if b != 1:        # a document per chunk: no later chunk in any document, dV^ is exactly 0
+            assert rel(f64(dV[b]), outs[b][1]) < TOL[dtype], b
+    assert not torch.any(dV[1])
+    assert rel(f64(dW0), sum(o[2] for o in outs)) < TOL[dtype]
+
+
 # the states the forward chunk loop keeps are the ones the backward recomputes, bit for bit (same operands, same
 # accumulation order), on the fused scan with segments, without, and on the delta + scan path
 @pytest.mark.parametrize("dtype,C,k", [("bf16", 128, 4), ("f32", 96, 3), ("bf16", 72, 2)])
