@@ -305,7 +305,7 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
     return O, W_final
 
 
-def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, dO):
+def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, dO, doc_starts=None):
     """Gradients of a loss that depends on the output O of the dot-objective
     layer (inplace_layer with mode "dot", the causal convolution, one document
     per row), given dO = dLoss/dO [B, n, d].  Returns (dH, dX0 [B, n, d],
@@ -325,7 +325,24 @@ def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, d
         dX0[s, i] = sum_j conv_w[i, j] dY[s + (K-1) - j, i] (rows outside
         the sequence contribute nothing).
     The weights are shared by the batch rows, so their gradients add over rows.
+
+    `doc_starts` [B, n_chunks] packs documents as in inplace_layer.  The
+    documents of a row are independent sequences (the state restarts from
+    W_down0 and the convolution from zeros at each start), so the row's
+    gradients are those of its documents taken one at a time: the activation
+    gradients side by side, the weight gradients added.
     """
+    if doc_starts is not None:
+        outs = []
+        for b in range(len(H)):
+            k = len(doc_starts[b])
+            cuts = [c * chunk for c in range(k) if c == 0 or doc_starts[b][c]] + [min(k * chunk, len(H[b]))]
+            parts = [layer_backward(H[b:b + 1, a:e], X0[b:b + 1, a:e], W_gate, W_up, W_down0, W_target, conv_w,
+                                    chunk, eta, dO[b:b + 1, a:e]) for a, e in zip(cuts[:-1], cuts[1:])]
+            outs.append((np.concatenate([q[0] for q in parts], axis=1), np.concatenate([q[1] for q in parts], axis=1),
+                         *[sum(q[i] for q in parts) for i in range(2, 7)]))
+        return (np.concatenate([o[0] for o in outs]), np.concatenate([o[1] for o in outs]),
+                *[sum(o[i] for o in outs) for i in range(2, 7)])
     H, X0, Wg, Wu, W0, Wt, cw, dO = map(_f64, (H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO))
     B, n, d = H.shape
     K = cw.shape[1]

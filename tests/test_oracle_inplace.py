@@ -698,3 +698,32 @@ def test_core_backward_with_documents_matches_autograd():
     O_docs = np.concatenate([orc.chunk_apply_update(Z[a:b], V[a:b], W0, C, eta, "dot")[0]
                              for a, b in ((0, 6), (6, 9), (9, 15))])
     np.testing.assert_allclose(O_loop, O_docs, rtol=1e-12, atol=1e-12)
+
+
+def test_layer_backward_with_documents_matches_autograd():
+    """Packed documents in the whole layer: autograd of the layer whose convolution restarts with zeros and whose
+    chunk loop restarts from W0 at each flagged chunk (torch's grouped conv1d per document)."""
+    import torch.nn.functional as F
+    rng = _rng(55)
+    B, n, C, d, f, K, eta = 2, 12, 3, 3, 4, 3, 0.2
+    starts = np.array([[1, 0, 1, 0], [1, 1, 0, 1]])
+    shapes = ((B, n, d), (B, n, d), (f, d), (f, d), (d, f), (d, d), (d, K))
+    args = [rng.standard_normal(s) * 0.7 for s in shapes]
+    dO = rng.standard_normal((B, n, d))
+    ours = orc.layer_backward(*args, C, eta, dO, doc_starts=starts)
+    ts = [torch.tensor(a, requires_grad=True) for a in args]
+    H, X0, Wg, Wu, W0, Wt, cw = ts
+    rows = []
+    for b in range(B):
+        outs, W = [], W0
+        cuts = [c * C for c in range(4) if starts[b][c]] + [n]
+        for a, e in zip(cuts[:-1], cuts[1:]):
+            Z = F.silu(H[b, a:e] @ Wg.T) * (H[b, a:e] @ Wu.T)
+            Y = F.conv1d(F.pad(X0[b, a:e].T[None], (K - 1, 0)), cw[:, None, :], groups=d)[0].T
+            outs.append(_torch_dot_chunk_loop(Z, Y @ Wt, W0, C, eta))
+        rows.append(torch.cat(outs))
+    (torch.stack(rows) * torch.from_numpy(dO)).sum().backward()
+    for got, t in zip(ours, ts):
+        np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-11, atol=1e-11)
+    O, _ = orc.inplace_layer(*args, C, eta, "dot", doc_starts=starts)
+    np.testing.assert_allclose(O, torch.stack(rows).detach().numpy(), rtol=1e-12, atol=1e-12)
