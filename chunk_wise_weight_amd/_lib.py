@@ -62,7 +62,7 @@ _SIGNATURES = {
                                       ctypes.POINTER(LayerOptions), _P, _P, _P, _S, _P]),
     "ttt_core_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
     "ttt_layer_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
-    "ttt_layer_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 17 + [_S, _P]),
+    "ttt_layer_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 18 + [_S, _P]),
     "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                                _P]),
     "ttt_produce_z": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P, _P]),
@@ -315,9 +315,10 @@ def ttt_layer_backward_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, 
 
 
 def ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk: int, eta: float, W_states=None,
-                       grads=None, workspace=None):
+                       grads=None, workspace=None, doc_starts=None):
     """Gradients of the dot layer with respect to every input, given dO = dLoss/dO [B, n, d], with the per-chunk
-    states W_states kept by the forward call or recomputed (None).  Returns (dH, dX0, dW_gate, dW_up, dW_down0,
+    states W_states kept by the forward call or recomputed (None), and doc_starts [B, n // chunk] packing documents
+    as for the forward layer.  Returns (dH, dX0, dW_gate, dW_up, dW_down0,
     dW_target, dconv_w): activations in the inputs' dtype, weight gradients fp32 summed over the batch rows."""
     B, n, d = H.shape
     f = W_gate.shape[0]
@@ -339,8 +340,10 @@ def ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk
     nbytes = ttt_layer_backward_workspace_bytes(shape, dt, W_states is not None)
     ws = _workspace(nbytes, dev, workspace)
     sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
+    doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
+    dp = ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None and doc_starts.numel() else None
     _check(lib().ttt_layer_backward(ctypes.byref(shape), _dt(dt), float(eta), _ptr(H), _ptr(X0), _ptr(W_gate),
-                                    _ptr(W_up), _ptr(W_down0), _ptr(W_target), _ptr(conv_w), _ptr(dO), sp,
+                                    _ptr(W_up), _ptr(W_down0), _ptr(W_target), _ptr(conv_w), _ptr(dO), sp, dp,
                                     *[_ptr(g) for g in grads], _ptr(ws), nbytes, _stream(dev)),
            "ttt_layer_backward")
     return grads

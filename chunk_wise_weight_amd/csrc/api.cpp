@@ -405,7 +405,7 @@ struct LayerBwdPlan {
 
 int make_layer_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, LayerBwdPlan* p) {
   *p = LayerBwdPlan{};
-  int st = make_bwd_plan(s, dtype, saved, &p->core);
+  int st = make_bwd_plan(s, dtype, saved, &p->core, true);
   if (st != TTT_OK) return st;
   if (!p->core.fused) return TTT_ERR_UNSUPPORTED;     // the weight gradients take the fused scan's token steps
   p->B = s->batch;
@@ -495,7 +495,7 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
   int st = dev(ttt::launch_zero<T>((T*)(ws + L.off_wzero), L.DFm, s));
   if (st == TTT_OK) st = dev(ttt::launch_produce_z<T>(H, Wg, Wu, Z, nullptr, rows, n, d, f, s));
   if (st == TTT_OK)
-    st = dev(ttt::launch_conv<T>((const T*)X0v, (const T*)cwv, Y, rows, n, d, K, nullptr, C, false, nullptr, s));
+    st = dev(ttt::launch_conv<T>((const T*)X0v, (const T*)cwv, Y, rows, n, d, K, L.core.docs, C, false, nullptr, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Wt, WtT, 1, d, d, 1.0f, 0, s));
   if (st == TTT_OK) st = dev(ttt::launch_apply<T>(Y, WtT, 0, 0, Vs, B, n, d, d, C, eta, s, true));
   // the chunk loop: dZ, dV^ and dW_down0
@@ -512,7 +512,8 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
   if (st == TTT_OK) st = dev(ttt::launch_sum_rows(wWf, dWt, B, (int64_t)d * d, s));
   if (st == TTT_OK) st = dev(ttt::launch_apply<T>(dV, Wt, 0, 0, dY, B, n, d, d, C, 1.0f, s, true));
   if (st == TTT_OK)
-    st = dev(ttt::launch_conv_bwd<T>((const T*)X0v, (const T*)cwv, dY, (T*)dX0v, part, rows, n, d, K, s));
+    st = dev(ttt::launch_conv_bwd<T>((const T*)X0v, (const T*)cwv, dY, (T*)dX0v, part, rows, n, d, K, s,
+                                     L.core.docs, C));
   if (st == TTT_OK) st = dev(ttt::launch_sum_rows(part, dcw, (int)L.npart, (int64_t)d * K, s));
   return st;
 }
@@ -654,12 +655,13 @@ int ttt_layer_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype
 
 int ttt_layer_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
                        const void* W_gate, const void* W_up, const void* W_down0, const void* W_target,
-                       const void* conv_w, const void* dO, const void* W_states, void* dH, void* dX0,
-                       float* dW_gate, float* dW_up, float* dW_down0, float* dW_target, float* dconv_w,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
+                       void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
+                       float* dconv_w, void* workspace, size_t workspace_bytes, void* stream) {
   LayerBwdPlan p;
   int st = make_layer_bwd_plan(shape, dtype, W_states != nullptr, &p);
   if (st != TTT_OK) return st;
+  p.core.docs = doc_starts;
   if (!finite(eta)) return TTT_ERR_ARG;
   if (!ok_ptr(dW_gate) || !ok_ptr(dW_up) || !ok_ptr(dW_down0) || !ok_ptr(dW_target) || !ok_ptr(dconv_w) ||
       (W_states != nullptr && !aligned16(W_states)))

@@ -124,17 +124,20 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
   }
 }
 
-// Backward of the causal convolution of k_conv (no document starts or halo):
-// dX0[s, ch] = sum_j conv_w[ch, j] dY[s + (KW-1) - j, ch], rows past the
-// sequence end zero; and dconv_w[ch, j] = sum_t dY[t, ch] X0[t - (KW-1) + j, ch],
-// rows before the sequence start zero.  One thread: one 16-byte channel chunk
+// Backward of the causal convolution of k_conv (no halo):
+// dX0[s, ch] = sum_j conv_w[ch, j] dY[s + (KW-1) - j, ch], rows past the end of
+// s's document zero; and dconv_w[ch, j] = sum_t dY[t, ch] X0[t - (KW-1) + j, ch],
+// rows before the start of t's document zero.  Documents start at chunk
+// boundaries and KW - 1 < C_, so a group's windows reach at most the next
+// chunk (dY) or the previous one (X0).  One thread: one 16-byte channel chunk
 // over kConvBwdGroups groups of kConvRows rows (each group inside one batch
 // row), writing its share of dconv_w to part [blocks, d, KW] (fp32), which a
 // row sum then reduces.
 template <typename T, int KW>
 __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ X0, const T* __restrict__ cw,
                                                   const T* __restrict__ dY, T* __restrict__ dX0,
-                                                  float* __restrict__ part, int64_t rows, int n, int d) {
+                                                  float* __restrict__ part, int64_t rows, int n, int d,
+                                                  const uint8_t* __restrict__ docs, int C_) {
   constexpr int V = Vec<T>::V, RW = kConvRows, NIN = RW + KW - 1;
   const int nchunk = d / V;
   const int64_t ngroups = rows / RW;
@@ -174,13 +177,20 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ X0, cons
     if (grp >= ngroups) break;
     const int64_t r0 = grp * RW;
     const int pos0 = (int)(r0 % n);
-    // gy[i]: dY row r0 + i (zero from the sequence end on); xs[i]: X0 row r0 - (KW-1) + i (zero before the start)
+    // this group's chunk and document bounds: lo = its document's first row if the chunk starts one (else the
+    // window never reaches back past the document's start); hi = the first row of the next document if the next
+    // chunk starts one (else the sequence end, or further)
+    const int64_t row = r0 / n;
+    const int kc = n / C_, c = pos0 / C_;
+    const int lo = doc_start(docs, row, kc, c) ? c * C_ : 0;
+    const int hi = c + 1 < kc && docs != nullptr && docs[row * kc + c + 1] != 0 ? (c + 1) * C_ : n;
+    // gy[i]: dY row r0 + i (zero from hi on); xs[i]: X0 row r0 - (KW-1) + i (zero before lo)
     u32x4 gy[NIN], xs[NIN];
 #pragma unroll
     for (int i = 0; i < NIN; ++i) {
-      gy[i] = pos0 + i < n ? *reinterpret_cast<const u32x4*>(dY + (r0 + i) * d + ch) : u32x4{0u, 0u, 0u, 0u};
-      xs[i] = pos0 + i - (KW - 1) >= 0 ? *reinterpret_cast<const u32x4*>(X0 + (r0 + i - (KW - 1)) * d + ch)
-                                       : u32x4{0u, 0u, 0u, 0u};
+      gy[i] = pos0 + i < hi ? *reinterpret_cast<const u32x4*>(dY + (r0 + i) * d + ch) : u32x4{0u, 0u, 0u, 0u};
+      xs[i] = pos0 + i - (KW - 1) >= lo ? *reinterpret_cast<const u32x4*>(X0 + (r0 + i - (KW - 1)) * d + ch)
+                                        : u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
@@ -1128,14 +1138,14 @@ hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int 
 
 template <typename T>
 hipError_t launch_conv_bwd(const T* X0, const T* cw, const T* dY, T* dX0, float* part, int64_t rows, int n, int d,
-                           int K, hipStream_t s) {
+                           int K, hipStream_t s, const uint8_t* docs, int C) {
   if (rows == 0) return hipSuccess;
   const int64_t threads = conv_bwd_partials(rows) * (d / Vec<T>::V);
   const dim3 g((unsigned)cdiv(threads, 256));
   switch (K) {
 #define TTT_KW(KW)                                                                                            \
   case KW:                                                                                                    \
-    k_conv_bwd<T, KW><<<g, 256, 0, s>>>(X0, cw, dY, dX0, part, rows, n, d);                                   \
+    k_conv_bwd<T, KW><<<g, 256, 0, s>>>(X0, cw, dY, dX0, part, rows, n, d, docs, C);                          \
     break;
     TTT_KW(1) TTT_KW(2) TTT_KW(3) TTT_KW(4) TTT_KW(5) TTT_KW(6) TTT_KW(7) TTT_KW(8)
 #undef TTT_KW
@@ -1322,7 +1332,7 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
   template hipError_t launch_produce_z_bwd<T>(const T*, const T*, const T*, const T*, T*, int64_t, int, int, int,  \
                                               hipStream_t);                                                       \
   template hipError_t launch_conv_bwd<T>(const T*, const T*, const T*, T*, float*, int64_t, int, int, int,        \
-                                         hipStream_t);                                                            \
+                                         hipStream_t, const uint8_t*, int);                                       \
   template hipError_t launch_zero<T>(T*, int64_t, hipStream_t);                                                   \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
                                           const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t,  \

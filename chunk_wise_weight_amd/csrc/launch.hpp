@@ -86,7 +86,7 @@ hipError_t launch_produce_z_bwd(const T* H, const T* Wg, const T* Wu, const T* d
 // partials part [conv_bwd_partials(rows), d, K] (fp32).
 template <typename T>
 hipError_t launch_conv_bwd(const T* X0, const T* cw, const T* dY, T* dX0, float* part, int64_t rows, int n, int d,
-                           int K, hipStream_t s);
+                           int K, hipStream_t s, const uint8_t* docs, int C);
 // Number of tap-gradient partials launch_conv_bwd writes: a thread takes
 // kConvBwdGroups groups of kConvBwdRows rows of one channel chunk.
 constexpr int kConvBwdRows = 8, kConvBwdGroups = 32;

@@ -253,8 +253,8 @@ int ttt_layer_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype
                                        size_t* bytes);
 
 /* Gradients of a loss that depends on the output O of the dot-objective layer
- * (ttt_chunk_apply_update with TTT_MODE_DOT, the causal convolution, one
- * document per row), given dO = dLoss/dO [B, n, d] (dtype), with respect to
+ * (ttt_chunk_apply_update with TTT_MODE_DOT and the causal convolution),
+ * given dO = dLoss/dO [B, n, d] (dtype), with respect to
  * every input (Method §1-§3, eq. (1)-(6), by the chain rule):
  *   dH, dX0            [B, n, d] dtype
  *   dW_gate, dW_up     [f, d] fp32      (sums over the batch rows, as for
@@ -269,15 +269,20 @@ int ttt_layer_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype
  * dW_gate = sum dA^T H, dW_up = sum dU^T H, dH = dA W_gate + dU W_up;
  * dW_target = sum Y^T dV^, dY = dV^ W_target^T; dconv_w[i, j] = sum_t dY[t, i]
  * X0[t - (K-1) + j, i] and dX0[s, i] = sum_j conv_w[i, j] dY[s + K-1-j, i].
+ * doc_starts [B, k] (DEVICE, as ttt_layer_options.doc_starts; NULL: one
+ * document per row) packs documents: each is differentiated as the
+ * independent sequence the forward call makes of it (the convolution and the
+ * states restart at its first chunk), and the weight gradients add over
+ * documents as over rows.
  * Token sums run in the fused scan's K steps, so chunk must be a multiple of
  * 64 (bf16) or 32 (fp32), else TTT_ERR_UNSUPPORTED.  batch == 0 or
  * seq_len == 0: every weight gradient is 0 and nothing else is touched.
  * Other rules as for every entry point. */
 int ttt_layer_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
                        const void* W_gate, const void* W_up, const void* W_down0, const void* W_target,
-                       const void* conv_w, const void* dO, const void* W_states, void* dH, void* dX0,
-                       float* dW_gate, float* dW_up, float* dW_down0, float* dW_target, float* dconv_w,
-                       void* workspace, size_t workspace_bytes, void* stream);
+                       const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
+                       void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
+                       float* dconv_w, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- the individual steps (each is one stage of the call above; they compose
  *      into it and exist for composition and per-step checks).  The updates

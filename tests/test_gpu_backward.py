@@ -212,6 +212,23 @@ def test_layer_backward_matches_oracle(dtype, C, k, K):
         assert rel(f64(got), want) < TOL[dtype], name
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_backward_packed_documents(dtype):
+    """Packed documents in the whole layer's backward: the convolution's gradient stops at document bounds and the
+    chunk loop's suffixes at document ends; row 0 packs documents of 2, 3 and 1 chunks, row 1 of 1, 2 and 3."""
+    cfg, x, dO = layer_case(dtype, 2, 6 * 128, 128, K=4)
+    starts = np.array([[1, 0, 1, 0, 0, 1], [1, 1, 0, 1, 0, 0]], dtype=np.uint8)
+    g = {name: t.cuda() for name, t in x.items()}
+    grads = cw.ttt_layer_backward(*layer_args(g), dO.cuda(), cfg.chunk, cfg.eta,
+                                  doc_starts=torch.from_numpy(starts).cuda())
+    torch.cuda.synchronize()
+    ref = orc.layer_backward(*(ti.to_f64(x[name]) for name in ("H", "X0", "W_gate", "W_up", "W_down0", "W_target",
+                                                               "conv_w")), cfg.chunk, cfg.eta, ti.to_f64(dO),
+                             doc_starts=starts)
+    for name, got, want in zip(GRAD_NAMES, grads, ref):
+        assert rel(f64(got), want) < TOL[dtype], name
+
+
 def test_layer_backward_with_kept_states():
     # the layer's forward keeps its states; the backward given them agrees with the recomputing one
     cfg, x, dO = layer_case("bf16", 2, 512, 128)
