@@ -244,6 +244,33 @@ def test_backward_workspace_and_validation():
     assert call(0.1, ins, None, outs, _fake(), _fake(), nb, dtype=7) == cw.TTT_ERR_DTYPE
 
 
+def test_layer_backward_validation():
+    """ttt_layer_backward validates before any device work: the fused scan's token step, pointers, eta, workspace."""
+    lib = cw.lib()
+    out = ctypes.c_size_t(0)
+    s = cw.InplaceShape(1, 2048, 256, 512, 256, 4)
+    assert lib.ttt_layer_backward_workspace_bytes(ctypes.byref(s), cw.TTT_BF16, 0, ctypes.byref(out)) == cw.TTT_OK
+    nb = out.value
+    kept = ctypes.c_size_t(0)
+    assert lib.ttt_layer_backward_workspace_bytes(ctypes.byref(s), cw.TTT_BF16, 1, ctypes.byref(kept)) == cw.TTT_OK
+    assert kept.value < nb            # kept states: no recomputed states in the workspace
+    odd = cw.InplaceShape(1, 2000, 256, 512, 40, 4)     # chunk 40: off the fused scan's 64-token steps
+    assert lib.ttt_layer_backward_workspace_bytes(ctypes.byref(odd), cw.TTT_BF16, 0,
+                                                  ctypes.byref(out)) == cw.TTT_ERR_UNSUPPORTED
+    ins = [_fake() for _ in range(8)]     # H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO
+    outs = [_fake() for _ in range(7)]    # dH, dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w
+
+    def call(eta, ins, outs, w, nbytes, shape=s):
+        return lib.ttt_layer_backward(ctypes.byref(shape), cw.TTT_BF16, eta, *ins, None, None, *outs, w, nbytes, None)
+
+    assert call(0.1, ins, outs, _fake(), nb - 1) == cw.TTT_ERR_WORKSPACE
+    assert call(0.1, ins, outs, None, nb) == cw.TTT_ERR_WORKSPACE
+    assert call(float("inf"), ins, outs, _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, ins[:6] + [None] + ins[7:], outs, _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, ins, outs[:6] + [ctypes.c_void_p(0x100004)], _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, ins, outs, _fake(), 1 << 40, shape=odd) == cw.TTT_ERR_UNSUPPORTED
+
+
 def test_forward_keeps_states_only_for_the_dot_objective():
     lib = cw.lib()
     s = cw.InplaceShape(1, 2048, 256, 512, 256, 4)
