@@ -46,7 +46,8 @@ import numpy as np
 __all__ = [
     "silu", "causal_depthwise_conv1d", "forward_chunk_conv1d", "target_values", "gated_intermediate",
     "gated_mlp", "loss_dot", "loss_mse", "grad_dot", "grad_mse",
-    "chunk_apply_update", "chunk_core_backward", "chunk_prefix_form", "inplace_layer", "layer_backward",
+    "chunk_apply_update", "chunk_core_backward", "mse_core_backward", "chunk_prefix_form", "inplace_layer",
+    "layer_backward",
 ]
 
 
@@ -211,6 +212,40 @@ def chunk_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None):
             dW0 = dW0 + S
             S = np.zeros_like(W0)
     return dZ, dV, dW0
+
+
+def mse_core_backward(Z, Vhat, W0, chunk, eta, dO):
+    """Gradients of a loss through the MSE chunk loop (chunk_apply_update with
+    mode "mse"), given dO = dLoss/dO: returns (dZ [n, f], dVhat [n, d],
+    dW0 [d, f]).  Per chunk (eq. (3)-(4)): O_c = Z_c W_c^T, R_c = Z_c W_c^T -
+    Vhat_c, W_{c+1} = W_c - (eta/C) R_c^T Z_c with C the chunk's tokens.  With
+    G = dLoss/dW_{c+1}, taken from the last chunk back (zero after it):
+      T_c      = dO_c - (eta/C) Z_c G^T
+      dZ_c     = T_c W_c - (eta/C) R_c G
+      dVhat_c  = (eta/C) Z_c G^T
+      dLoss/dW_c = G + T_c^T Z_c,
+    and dW0 is dLoss/dW_0.  The loss is taken to depend on O only."""
+    Z, Vhat, W0, dO = _f64(Z), _f64(Vhat), _f64(W0), _f64(dO)
+    n = Z.shape[0]
+    bounds = [(s, min(s + chunk, n)) for s in range(0, n, chunk)]
+    states = []
+    W = W0.copy()
+    for (s, e) in bounds:                         # the forward scan, keeping the state each chunk saw
+        states.append(W)
+        W = W - eta * grad_mse(W, Z[s:e], Vhat[s:e])
+    dZ = np.empty_like(Z)
+    dV = np.empty_like(Vhat)
+    G = np.zeros_like(W0)
+    for c in range(len(bounds) - 1, -1, -1):
+        s, e = bounds[c]
+        Zc, Wc, a = Z[s:e], states[c], eta / (e - s)
+        R = Zc @ Wc.T - Vhat[s:e]
+        Q = Zc @ G.T
+        T = dO[s:e] - a * Q
+        dZ[s:e] = T @ Wc - a * (R @ G)
+        dV[s:e] = a * Q
+        G = G + T.T @ Zc
+    return dZ, dV, G
 
 
 def chunk_prefix_form(Z, Vhat, W0, chunk, eta):

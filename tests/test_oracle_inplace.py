@@ -727,3 +727,32 @@ def test_layer_backward_with_documents_matches_autograd():
         np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-11, atol=1e-11)
     O, _ = orc.inplace_layer(*args, C, eta, "dot", doc_starts=starts)
     np.testing.assert_allclose(O, torch.stack(rows).detach().numpy(), rtol=1e-12, atol=1e-12)
+
+
+def _torch_mse_chunk_loop(Z, V, W0, C, eta):
+    """The MSE chunk loop in torch float64 (apply, then the step on the chunk's mean squared error), for autograd."""
+    W = W0
+    outs = []
+    for s in range(0, Z.shape[0], C):
+        Zc, Vc = Z[s:s + C], V[s:s + C]
+        O = Zc @ W.T
+        outs.append(O)
+        W = W - (eta / Zc.shape[0]) * ((O - Vc).T @ Zc)
+    return torch.cat(outs)
+
+
+@pytest.mark.parametrize("n,C", [(12, 4), (10, 3), (8, 8)])
+def test_mse_core_backward_matches_autograd(n, C):
+    """The MSE chunk loop's backward against torch autograd of the same loop (ragged last chunk, one chunk)."""
+    rng = _rng(56)
+    d, f, eta = 3, 5, 0.4
+    Z, V, W0, dO = (rng.standard_normal(s) for s in ((n, f), (n, d), (d, f), (n, d)))
+    dZ, dV, dW0 = orc.mse_core_backward(Z, V, W0, C, eta, dO)
+    tz, tv, tw = (torch.tensor(a, requires_grad=True) for a in (Z, V, W0))
+    (_torch_mse_chunk_loop(tz, tv, tw, C, eta) * torch.from_numpy(dO)).sum().backward()
+    grad = lambda t: np.zeros(t.shape) if t.grad is None else t.grad.numpy()
+    np.testing.assert_allclose(dZ, grad(tz), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dV, grad(tv), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dW0, grad(tw), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(_torch_mse_chunk_loop(tz, tv, tw, C, eta).detach().numpy(),
+                               orc.chunk_apply_update(Z, V, W0, C, eta, "mse")[0], rtol=1e-12, atol=1e-12)
