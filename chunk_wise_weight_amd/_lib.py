@@ -61,6 +61,8 @@ _SIGNATURES = {
     "ttt_core_apply_update_ex": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P,
                                       ctypes.POINTER(LayerOptions), _P, _P, _P, _S, _P]),
     "ttt_core_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
+    "ttt_core_backward_mse_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, ctypes.POINTER(_S)]),
+    "ttt_core_backward_mse": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "ttt_layer_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
     "ttt_layer_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 18 + [_S, _P]),
     "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
@@ -303,6 +305,40 @@ def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVh
                                    _ptr(dO), sp, dp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
                                    _stream(dev)),
            "ttt_core_backward")
+    return dZ, dVhat, dW_down0
+
+
+def ttt_core_backward_mse_workspace_bytes(shape: InplaceShape, dtype: torch.dtype) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().ttt_core_backward_mse_workspace_bytes(ctypes.byref(shape), _dt(dtype), ctypes.byref(n)),
+           "ttt_core_backward_mse_workspace_bytes")
+    return n.value
+
+
+def ttt_core_backward_mse(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVhat=None, dW_down0=None,
+                          workspace=None):
+    """Gradients through the MSE chunk loop given dO = dLoss/dO [B, n, d].
+    Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
+    B, n, f = Z.shape
+    d = Vhat.shape[2]
+    dt, dev = Z.dtype, Z.device
+    _need(Z, "Z", (B, n, f), dt, dev)
+    _need(Vhat, "Vhat", (B, n, d), dt, dev)
+    _need(W_down0, "W_down0", (d, f), dt, dev)
+    _need(dO, "dO", (B, n, d), dt, dev)
+    shape = _inplace_shape(B, n, d, f, chunk, 1)
+    dZ = torch.empty(B, n, f, dtype=dt, device=dev) if dZ is None else dZ
+    dVhat = torch.empty(B, n, d, dtype=dt, device=dev) if dVhat is None else dVhat
+    dW_down0 = torch.empty(d, f, dtype=torch.float32, device=dev) if dW_down0 is None else dW_down0
+    _need(dZ, "dZ", (B, n, f), dt, dev)
+    _need(dVhat, "dVhat", (B, n, d), dt, dev)
+    _need(dW_down0, "dW_down0", (d, f), torch.float32, dev)
+    nbytes = ttt_core_backward_mse_workspace_bytes(shape, dt)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib().ttt_core_backward_mse(ctypes.byref(shape), _dt(dt), float(eta), _ptr(Z), _ptr(Vhat), _ptr(W_down0),
+                                       _ptr(dO), _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
+                                       _stream(dev)),
+           "ttt_core_backward_mse")
     return dZ, dVhat, dW_down0
 
 

@@ -386,6 +386,106 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
   return st;
 }
 
+// ------------------------------------------------------------------ backward of the MSE chunk loop
+
+// Workspace of ttt_core_backward_mse: token-contiguous Z, V^ and dO, the state
+// each chunk was applied with ([k, B, d, f], chunk-major so that one chunk's
+// states are one block), the forward state and the state gradient (fp32, with
+// bf16 operand copies), and one chunk's two residual buffers [B, d, C].
+struct MsePlan {
+  int64_t B, n, d, f, C, k;
+  size_t esz;
+  size_t off_Zt, off_Vt, off_Gt, off_St, off_Ws, off_Wsh, off_G, off_Gsh, off_Rt, off_Tt, total;
+};
+
+int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p) {
+  int st = check_inplace_shape(s, dtype);
+  if (st != TTT_OK) return st;
+  *p = MsePlan{};
+  p->B = s->batch;
+  p->n = s->seq_len;
+  p->d = s->d_model;
+  p->f = s->d_ff;
+  p->C = s->chunk;
+  p->k = s->seq_len / s->chunk;
+  p->esz = dtype == TTT_BF16 ? 2 : 4;
+  if (p->B * p->n == 0) return TTT_OK;
+  const size_t BN = (size_t)p->B * p->n, DF = (size_t)p->d * p->f, e = p->esz, B = (size_t)p->B;
+  size_t off = 0;
+  auto take = [&](size_t* o, size_t bytes) {
+    *o = off;
+    off += align_up(bytes);
+  };
+  take(&p->off_Zt, BN * p->f * e);
+  take(&p->off_Vt, BN * p->d * e);
+  take(&p->off_Gt, BN * p->d * e);
+  take(&p->off_St, (size_t)p->k * B * DF * e);
+  take(&p->off_Ws, B * DF * 4);
+  take(&p->off_G, B * DF * 4);
+  if (dtype == TTT_BF16) {
+    take(&p->off_Wsh, B * DF * e);
+    take(&p->off_Gsh, B * DF * e);
+  }
+  take(&p->off_Rt, B * p->d * p->C * e);
+  take(&p->off_Tt, B * p->d * p->C * e);
+  p->total = off;
+  return TTT_OK;
+}
+
+template <typename T>
+int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, const void* W0v, const void* dOv,
+                 void* dZv, void* dVv, float* dW0, char* ws, hipStream_t s) {
+  const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
+  const int64_t df = (int64_t)d * f;
+  if (p.B * p.n == 0) return dev(ttt::launch_zero<float>(dW0, df, s));
+  const bool bf = sizeof(T) == 2;
+  const T* W0 = (const T*)W0v;
+  T* Zt = (T*)(ws + p.off_Zt);
+  T* Vt = (T*)(ws + p.off_Vt);
+  T* Gt = (T*)(ws + p.off_Gt);
+  T* St = (T*)(ws + p.off_St);
+  float* Ws = (float*)(ws + p.off_Ws);
+  float* G = (float*)(ws + p.off_G);
+  T* Wsh = bf ? (T*)(ws + p.off_Wsh) : nullptr;
+  T* Gsh = bf ? (T*)(ws + p.off_Gsh) : nullptr;
+  const T* Wcur = bf ? (const T*)Wsh : (const T*)(const void*)Ws;       // the state operand the applies read
+  const T* Gop = bf ? (const T*)Gsh : (const T*)(const void*)G;
+  T* Rt = (T*)(ws + p.off_Rt);
+  T* Tt = (T*)(ws + p.off_Tt);
+  const float a = eta / (float)C;
+  int st = dev(ttt::launch_transpose<T>((const T*)Zv, Zt, B, n, f, 1.0f, 0, s));
+  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Vv, Vt, B, n, d, 1.0f, 0, s));
+  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)dOv, Gt, B, n, d, 1.0f, 0, s));
+  // the forward scan again, keeping the state each chunk is applied with (chunk c >= 1: St[c])
+  for (int c = 0; c < k && st == TTT_OK; ++c) {
+    st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Ws, Wsh, nullptr, Rt, nullptr, false, B, n, d, f, C, c, eta,
+                                      s));
+    if (st == TTT_OK && c + 1 < k)
+      st = dev(ttt::launch_scale<T>(Wcur, St + (int64_t)(c + 1) * B * df, (int64_t)B * df, 1.0f, s));
+  }
+  // the state gradient G = dLoss/dW_{c+1}, zero after the last chunk, taken back chunk by chunk
+  if (st == TTT_OK) st = dev(ttt::launch_zero<float>(G, (int64_t)B * df, s));
+  if (st == TTT_OK && bf) st = dev(ttt::launch_zero<T>(Gsh, (int64_t)B * df, s));
+  for (int c = k - 1; c >= 0 && st == TTT_OK; --c) {
+    const T* Wc = St + (int64_t)c * B * df;                 // read for c >= 1; chunk 0 takes W_down0
+    // Rt = -(eta/C) R_c^T, R_c = Z_c W_c^T - V^_c
+    st = dev(ttt::launch_mse_apply_gen<T>(Zt, Vt, W0, Wc, nullptr, Rt, false, B, n, d, f, C, c, -a, 0.f, 1.f, false,
+                                          s));
+    // Tt = T_c^T = (dO_c - (eta/C) Z_c G^T)^T, and dV^_c = (eta/C) Z_c G^T
+    if (st == TTT_OK)
+      st = dev(ttt::launch_mse_apply_gen<T>(Zt, Gt, W0, Gop, (T*)dVv, Tt, true, B, n, d, f, C, c, -a, 1.0f, a, true,
+                                            s));
+    // dZ_c = T_c W_c - (eta/C) R_c G
+    if (st == TTT_OK)
+      st = dev(ttt::launch_dz_chunk<T>(Tt, Rt, c == 0 ? W0 : Wc, c == 0 ? 0 : df, Gop, df, (T*)dZv, B, n, d, f, C, c,
+                                       s));
+    // G <- G + T_c^T Z_c = dLoss/dW_c
+    if (st == TTT_OK) st = dev(ttt::launch_mse_update<T>(Zt, Tt, W0, G, Gsh, true, B, n, d, f, C, c, s));
+  }
+  if (st == TTT_OK) st = dev(ttt::launch_sum_rows(G, dW0, B, df, s));
+  return st;
+}
+
 // ------------------------------------------------------------------ backward of the whole dot layer
 
 // Workspace of ttt_layer_backward: the recomputed Z and Y, W_target^T, the
@@ -642,6 +742,33 @@ int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, cons
   if (dtype == TTT_BF16)
     return core_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
   return core_backward<float>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
+}
+
+int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_ARG;
+  MsePlan p;
+  int st = make_mse_plan(shape, dtype, &p);
+  if (st != TTT_OK) return st;
+  *bytes = p.total;
+  return TTT_OK;
+}
+
+int ttt_core_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
+                          const void* W_down0, const void* dO, void* dZ, void* dVhat, float* dW_down0,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  MsePlan p;
+  int st = make_mse_plan(shape, dtype, &p);
+  if (st != TTT_OK) return st;
+  if (!finite(eta) || !ok_ptr(dW_down0)) return TTT_ERR_ARG;
+  if (p.B * p.n > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(W_down0) || !ok_ptr(dO) || !ok_ptr(dZ) ||
+                        !ok_ptr(dVhat)))
+    return TTT_ERR_ARG;
+  if (p.total > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < p.total))
+    return TTT_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == TTT_BF16)
+    return mse_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, dZ, dVhat, dW_down0, (char*)workspace, s);
+  return mse_backward<float>(p, eta, Z, Vhat, W_down0, dO, dZ, dVhat, dW_down0, (char*)workspace, s);
 }
 
 int ttt_layer_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states, size_t* bytes) {

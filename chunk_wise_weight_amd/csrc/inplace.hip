@@ -870,11 +870,13 @@ struct Concat {
 // eta V^ and dO, [n, d]), K = d_model twice: one stream of K steps over
 // (S_j, eta V^_j), then (W_j, dO_j).  State j sits at W + b wsb + j wsc (S
 // likewise; its stride may be negative).  dZ [B, n, f] through LDS like O.
-// The rows of V and dO are ldq elements apart (d for [n, d] matrices).
-template <typename T>
+// The rows of V and dO are ldq elements apart (d for [n, d] matrices).  QT:
+// V and dO are one chunk's token-contiguous [B, d, C] buffers instead (read
+// MN-major), and the launch covers chunk cfix of every row only.
+template <typename T, bool QT>
 TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ V, const T* __restrict__ W,
                                 int64_t wsb, int64_t wsc, const T* __restrict__ S, int64_t ssb, int64_t ssc,
-                                T* __restrict__ dZ, int n, int d, int f, int C_, int ldq) {
+                                T* __restrict__ dZ, int n, int d, int f, int C_, int ldq, int cfix) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (f + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
@@ -883,8 +885,8 @@ TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ 
   const int bc = id / per;
   int tp, tq;
   grouped_tile(id - bc * per, TP, TQ, 4, tp, tq);
-  const int k = n / C_;
-  const int b = bc / k, c = bc - b * k;
+  const int k = QT ? 1 : n / C_;
+  const int b = bc / k, c = QT ? cfix : bc - b * k;
   const int j0 = tp * G::BP, t0 = tq * G::BQ;
   const int64_t row0 = (int64_t)b * n + (int64_t)c * C_ + t0;
   const uint64_t ldd = (uint64_t)d * esz<T>(), ldf = (uint64_t)f * esz<T>();
@@ -893,12 +895,18 @@ TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ 
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   Concat<DmaOpMN<T, G::NW, G::BP>> op;
-  Concat<DmaOp<G::NW, G::BQ>> oq;
+  std::conditional_t<QT, Concat<DmaOpMN<T, G::NW, G::BQ>>, Concat<DmaOp<G::NW, G::BQ>>> oq;
   op.a.init(S + (int64_t)b * ssb + (int64_t)c * ssc + j0, min(G::BP, f - j0), ldf, d);
   op.b.init(W + (int64_t)b * wsb + (int64_t)c * wsc + j0, min(G::BP, f - j0), ldf, d);
-  const uint64_t ldqb = (uint64_t)ldq * esz<T>();
-  oq.a.init(V + row0 * ldq, nullptr, min(G::BQ, C_ - t0), ldqb, (unsigned)ldd);
-  oq.b.init(dO + row0 * ldq, nullptr, min(G::BQ, C_ - t0), ldqb, (unsigned)ldd);
+  if constexpr (QT) {
+    const int64_t q0 = (int64_t)b * d * C_ + t0;               // chunk buffers [B, d, C]
+    oq.a.init(V + q0, min(G::BQ, C_ - t0), (uint64_t)C_ * esz<T>(), d);
+    oq.b.init(dO + q0, min(G::BQ, C_ - t0), (uint64_t)C_ * esz<T>(), d);
+  } else {
+    const uint64_t ldqb = (uint64_t)ldq * esz<T>();
+    oq.a.init(V + row0 * ldq, nullptr, min(G::BQ, C_ - t0), ldqb, (unsigned)ldd);
+    oq.b.init(dO + row0 * ldq, nullptr, min(G::BQ, C_ - t0), ldqb, (unsigned)ldd);
+  }
   op.n1 = oq.n1 = nks;
   mainloop<T, G>(op, oq, 2 * nks, acc, smem, NoHook{});
 
@@ -971,11 +979,14 @@ __global__ __launch_bounds__(256) void k_zero(T* __restrict__ p, int64_t n) {
 // W + Rt Z_c.  P = d_model rows of W (W_down0 where a document starts, else this row's state
 // copy), Q = the chunk's tokens, read from Zt [B, f, n] as an MN-major operand,
 // K = d_ff.
-template <typename T>
+// GEN (the MSE loop's backward): Rt = rscale O + vscale V^ instead, and O, if
+// not null, is written scaled by oscale; O may be null in either form.
+template <typename T, bool GEN>
 TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __restrict__ W0,
                                        const T* __restrict__ Wcur, T* __restrict__ O, const T* __restrict__ Vt,
                                        T* __restrict__ Rt, const uint8_t* __restrict__ docs, int n, int d, int f,
-                                       int C_, int c, float rscale, bool cont, const uint8_t* __restrict__ umask) {
+                                       int C_, int c, float rscale, bool cont, const uint8_t* __restrict__ umask,
+                                       float vscale, float oscale) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
@@ -1003,7 +1014,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
   const int tn = min(G::BQ, C_ - t0), in_ = min(G::BP, d - i0);
 
   // O [token, channel]: staged as [token][channel], in passes over token rows
-  {
+  if (O != nullptr) {
     constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
     const Staged<T, G::BP> st{smem};
 #pragma unroll
@@ -1013,8 +1024,10 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
         const int q = G::acc_q(j) - ps * RPP;
         if (q < 0 || q >= RPP) continue;
 #pragma unroll
-        for (int i = 0; i < G::NPB; ++i)
-          st.put4(q, G::acc_p(i, 0), acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+        for (int i = 0; i < G::NPB; ++i) {
+          const float os = GEN ? oscale : 1.0f;
+          st.put4(q, G::acc_p(i, 0), os * acc[i][j][0], os * acc[i][j][1], os * acc[i][j][2], os * acc[i][j][3]);
+        }
       }
       __syncthreads();
       st.template flush<G::NT>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
@@ -1055,10 +1068,17 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
         const f32x4 o1 = *reinterpret_cast<const f32x4*>(smem + st.off(r, t + 4));
         const f32x4 v0 = load4(vt + ch * n + t), v1 = load4(vt + ch * n + t + 4);
         T* dst = rt + ch * C_ + t;
-        store4(dst, rscale * (o0[0] - v0[0]), rscale * (o0[1] - v0[1]), rscale * (o0[2] - v0[2]),
-               rscale * (o0[3] - v0[3]));
-        store4(dst + 4, rscale * (o1[0] - v1[0]), rscale * (o1[1] - v1[1]), rscale * (o1[2] - v1[2]),
-               rscale * (o1[3] - v1[3]));
+        if constexpr (GEN) {
+          store4(dst, rscale * o0[0] + vscale * v0[0], rscale * o0[1] + vscale * v0[1],
+                 rscale * o0[2] + vscale * v0[2], rscale * o0[3] + vscale * v0[3]);
+          store4(dst + 4, rscale * o1[0] + vscale * v1[0], rscale * o1[1] + vscale * v1[1],
+                 rscale * o1[2] + vscale * v1[2], rscale * o1[3] + vscale * v1[3]);
+        } else {
+          store4(dst, rscale * (o0[0] - v0[0]), rscale * (o0[1] - v0[1]), rscale * (o0[2] - v0[2]),
+                 rscale * (o0[3] - v0[3]));
+          store4(dst + 4, rscale * (o1[0] - v1[0]), rscale * (o1[1] - v1[1]), rscale * (o1[2] - v1[2]),
+                 rscale * (o1[3] - v1[3]));
+        }
       }
       __syncthreads();
     }
@@ -1259,7 +1279,39 @@ hipError_t launch_dz(const T* dO, const T* V, const T* W, int64_t wsb, int64_t w
                      int64_t ssc, T* dZ, int B, int n, int d, int f, int Cs, hipStream_t s, int ldq) {
   const int64_t tiles = cdiv(f, kWB) * cdiv(Cs, kWB) * B * (n / Cs);
   if (tiles == 0) return hipSuccess;
-  k_dz<T><<<tiles_u(tiles), Wide::NT, 0, s>>>(dO, V, W, wsb, wsc, S, ssb, ssc, dZ, n, d, f, Cs, ldq > 0 ? ldq : d);
+  k_dz<T, false><<<tiles_u(tiles), Wide::NT, 0, s>>>(dO, V, W, wsb, wsc, S, ssb, ssc, dZ, n, d, f, Cs,
+                                                      ldq > 0 ? ldq : d, 0);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dz_chunk(const T* Tt, const T* Rt, const T* W, int64_t wsb, const T* S, int64_t ssb, T* dZ, int B,
+                           int n, int d, int f, int Cs, int c, hipStream_t s) {
+  const int64_t tiles = cdiv(f, kWB) * cdiv(Cs, kWB) * B;
+  if (tiles == 0) return hipSuccess;
+  k_dz<T, true><<<tiles_u(tiles), Wide::NT, 0, s>>>(Tt, Rt, W, wsb, 0, S, ssb, 0, dZ, n, d, f, Cs, d, c);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_mse_apply_gen(const T* Zt, const T* Vt, const T* W0, const T* Wcur, T* O, T* Rt, bool cont, int B,
+                                int n, int d, int f, int Cs, int c, float rscale, float vscale, float oscale, bool gen,
+                                hipStream_t s) {
+  const unsigned g = tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B);
+  if (gen)
+    k_mse_apply<T, true><<<g, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, nullptr, n, d, f, Cs, c, rscale, cont,
+                                                nullptr, vscale, oscale);
+  else
+    k_mse_apply<T, false><<<g, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, nullptr, n, d, f, Cs, c, rscale, cont,
+                                                 nullptr, 0.f, 1.f);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_mse_update(const T* Zt, const T* Rt, const T* W0, float* Ws, T* Wsh, bool cont, int B, int n, int d,
+                             int f, int Cs, int c, hipStream_t s) {
+  k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, nullptr, n, d, f,
+                                                                               Cs, c, cont);
   return hipGetLastError();
 }
 
@@ -1280,8 +1332,8 @@ template <typename T>
 hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
                             T* Rt, const uint8_t* docs, bool cont, int B, int n, int d, int f, int Cs, int c,
                             float eta, hipStream_t s, const uint8_t* umask) {
-  k_mse_apply<T><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, docs, n, d,
-                                                                              f, Cs, c, -eta / (float)Cs, cont, umask);
+  k_mse_apply<T, false><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(
+      Zt, W0, Wcur, O, Vt, Rt, docs, n, d, f, Cs, c, -eta / (float)Cs, cont, umask, 0.f, 1.f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, docs, n, d, f,
@@ -1329,6 +1381,12 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
   template hipError_t launch_scale<T>(const T*, T*, int64_t, float, hipStream_t);                                 \
   template hipError_t launch_dz<T>(const T*, const T*, const T*, int64_t, int64_t, const T*, int64_t, int64_t, T*, \
                                    int, int, int, int, int, hipStream_t, int);                                    \
+  template hipError_t launch_dz_chunk<T>(const T*, const T*, const T*, int64_t, const T*, int64_t, T*, int, int,  \
+                                         int, int, int, int, hipStream_t);                                        \
+  template hipError_t launch_mse_apply_gen<T>(const T*, const T*, const T*, const T*, T*, T*, bool, int, int, int, \
+                                              int, int, int, float, float, float, bool, hipStream_t);             \
+  template hipError_t launch_mse_update<T>(const T*, const T*, const T*, float*, T*, bool, int, int, int, int, int, \
+                                           int, hipStream_t);                                                     \
   template hipError_t launch_produce_z_bwd<T>(const T*, const T*, const T*, const T*, T*, int64_t, int, int, int,  \
                                               hipStream_t);                                                       \
   template hipError_t launch_conv_bwd<T>(const T*, const T*, const T*, T*, float*, int64_t, int, int, int,        \

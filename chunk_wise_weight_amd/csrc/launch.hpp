@@ -77,6 +77,23 @@ hipError_t launch_dz(const T* dO, const T* V, const T* W, int64_t wsb, int64_t w
 // out [df] = sum over b of Tot [B rows, `stride` apart; stride 0: df] (fp32;
 // df and stride multiples of 4).
 hipError_t launch_sum_rows(const float* Tot, float* out, int B, int64_t df, hipStream_t s, int64_t stride = 0);
+// The MSE loop's backward, one chunk c at a time: dZ_c = Tt^T W + Rt^T S with
+// Tt, Rt one chunk's token-contiguous [B, d, C] buffers, W at W + b wsb and S
+// at S + b ssb ([d, f] each).
+template <typename T>
+hipError_t launch_dz_chunk(const T* Tt, const T* Rt, const T* W, int64_t wsb, const T* S, int64_t ssb, T* dZ, int B,
+                           int n, int d, int f, int C, int c, hipStream_t s);
+// The MSE apply alone for chunk c: Rt = rscale (O - V^)^T, or with gen
+// rscale O^T + vscale V^T and O (if not null) scaled by oscale; the state is
+// W_down0 at chunk 0 unless cont, else Wcur + b d f.
+template <typename T>
+hipError_t launch_mse_apply_gen(const T* Zt, const T* Vt, const T* W0, const T* Wcur, T* O, T* Rt, bool cont, int B,
+                                int n, int d, int f, int C, int c, float rscale, float vscale, float oscale, bool gen,
+                                hipStream_t s);
+// The MSE update alone: Ws (and Wsh) = Ws + Rt Z_c, seeded from W_down0 at chunk 0 unless cont.
+template <typename T>
+hipError_t launch_mse_update(const T* Zt, const T* Rt, const T* W0, float* Ws, T* Wsh, bool cont, int B, int n, int d,
+                             int f, int C, int c, hipStream_t s);
 // Backward of the producer: G [rows, 2f] = [dA | dU] from dZ [rows, f],
 // recomputing A = H W_gate^T and U = H W_up^T.
 template <typename T>

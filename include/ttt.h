@@ -243,6 +243,31 @@ int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, cons
                       void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* Workspace bytes for ttt_core_backward_mse: about B (k d f + 2 n d + n f)
+ * dtype elements plus 2 B d f fp32. */
+int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes);
+
+/* Gradients through the MSE chunk loop (ttt_core_apply_update with
+ * TTT_MODE_MSE), for a loss that depends on O alone, given dO = dLoss/dO
+ * [B, n, d] (dtype).  Per chunk (eq. (3)-(4)): O_c = Z_c W_c^T, R_c = Z_c W_c^T
+ * - V^_c, W_{c+1} = W_c - (eta/C) R_c^T Z_c.  With G = dLoss/dW_{c+1} (zero
+ * after the last chunk), taken from the last chunk back:
+ *   T_c = dO_c - (eta/C) Z_c G^T
+ *   dZ_c = T_c W_c - (eta/C) R_c G          [B, n, f] dtype
+ *   dVhat_c = (eta/C) Z_c G^T               [B, n, d] dtype
+ *   dLoss/dW_c = G + T_c^T Z_c;  dW_down0 = its sum over the rows at c = 0
+ *                                           [d, f] fp32
+ * The call first runs the forward scan again and keeps the state each chunk
+ * was applied with (bf16 copies with bf16), then the reverse recursion: per
+ * chunk the MSE apply twice (for R_c, and for T_c with dVhat_c), the
+ * two-contraction dZ kernel, and the MSE update seeded with G.  Rows are
+ * single documents (no document starts, resumed state or update mask).
+ * seq_len == 0 or batch == 0 gives dW_down0 = 0.  Errors as for every entry
+ * point. */
+int ttt_core_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
+                          const void* W_down0, const void* dO, void* dZ, void* dVhat, float* dW_down0,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- backward of the whole dot layer ---- */
 
 /* Workspace bytes for ttt_layer_backward (saved_states as for

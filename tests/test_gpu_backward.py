@@ -277,3 +277,42 @@ def test_full_size_layer_backward_sampled():
     assert rel(got[3][P], ref[3]) < TOL["bf16"]
     assert rel(got[4][:, P], ref[4]) < TOL["bf16"]
     assert all(np.all(np.isfinite(t)) for t in got)
+
+
+# ---------------------------------------------------------------- the MSE chunk loop
+
+def mse_run(cfg):
+    x = ti.backward_inputs(cfg)
+    g = {name: t.cuda() for name, t in x.items()}
+    dZ, dV, dW0 = cw.ttt_core_backward_mse(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta)
+    torch.cuda.synchronize()
+    Z, V, W0, dO = (ti.to_f64(x[name]) for name in ("Z", "Vhat", "W_down0", "dO"))
+    outs = [orc.mse_core_backward(Z[b], V[b], W0, cfg.chunk, cfg.eta, dO[b]) for b in range(cfg.batch)]
+    ref = (np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]), sum(o[2] for o in outs))
+    return (f64(dZ), f64(dV), f64(dW0)), ref
+
+
+@pytest.mark.parametrize("dtype,C,k", [("f32", 96, 3), ("bf16", 128, 4), ("bf16", 72, 3), ("f32", 40, 2)])
+def test_mse_backward_matches_oracle(dtype, C, k):
+    cfg = cfg_of(dtype, 2, k, C, eta=0.5)
+    got, ref = mse_run(cfg)
+    for name, a, b in zip(("dZ", "dVhat", "dW_down0"), got, ref):
+        assert rel(a, b) < TOL[dtype], name
+
+
+def test_mse_backward_single_chunk_and_eta_zero():
+    got, ref = mse_run(cfg_of("bf16", 2, 1, 256, eta=0.5))      # one chunk: no later state, dVhat exactly 0
+    assert not np.any(got[1])
+    assert rel(got[0], ref[0]) < TOL["bf16"] and rel(got[2], ref[2]) < TOL["bf16"]
+    got, ref = mse_run(cfg_of("f32", 2, 3, 64, eta=0.0))        # eta = 0: dZ = dO W_down0, dVhat = 0
+    assert not np.any(got[1])
+    assert rel(got[0], ref[0]) < TOL["f32"] and rel(got[2], ref[2]) < TOL["f32"]
+
+
+def test_mse_backward_reduced_workload():
+    """The MSE workload's row count and eta at a size the oracle's fp64 loop finishes quickly: 4 rows of 4096
+    tokens, d 512, d_ff 2048, chunk 512 (8 chunks)."""
+    cfg = ti.workload("mse_bf16_4x64k").with_(seq_len=4096, d_model=512, d_ff=2048, chunk=512, backward=True)
+    got, ref = mse_run(cfg)
+    for name, a, b in zip(("dZ", "dVhat", "dW_down0"), got, ref):
+        assert rel(a, b) < TOL["bf16"], name
