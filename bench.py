@@ -176,16 +176,22 @@ def bench_generic(cfg, steps, warmup):
         dW0 = torch.empty(d, f, dtype=torch.float32, device="cuda")
         shape = cw.InplaceShape(B, n, d, f, cfg.chunk, 1)
         Ws = None
-        if cfg.kept_states:
+        if cfg.mode == "mse":
+            nbytes = cw.ttt_core_backward_mse_workspace_bytes(shape, dt)
+            ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
+            call = lambda: cw.ttt_core_backward_mse(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta, dZ,
+                                                    dV, dW0, ws)
+        elif cfg.kept_states:
             # the forward chunk loop keeps its states (before the timed region, like the other inputs)
             Ws = torch.empty(B, n // cfg.chunk, d, f, dtype=dt, device="cuda")
             cw.ttt_core_apply_update(g["Z"], g["Vhat"], g["W_down0"], cfg.chunk, cfg.eta, "dot", W_states=Ws)
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
-        nbytes = cw.ttt_core_backward_workspace_bytes(shape, dt, cfg.kept_states)
-        ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
-        call = lambda: cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta, dZ, dV,
-                                            dW0, ws, W_states=Ws)
+        if cfg.mode != "mse":
+            nbytes = cw.ttt_core_backward_workspace_bytes(shape, dt, cfg.kept_states)
+            ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
+            call = lambda: cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta, dZ, dV,
+                                                dW0, ws, W_states=Ws)
     elif isinstance(cfg, ti.LactConfig):
         x = ti.lact_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
@@ -260,8 +266,9 @@ def cpu_baseline(cfg, target_s):
     elif cfg.backward:
         x = ti.backward_inputs(cfg)
         W0 = ti.to_f64(x["W_down0"])
-        run = lambda kc: orc.chunk_core_backward(*(ti.to_f64(x[k][0, : kc * cfg.chunk]) for k in ("Z", "Vhat")), W0,
-                                                 cfg.chunk, cfg.eta, ti.to_f64(x["dO"][0, : kc * cfg.chunk]))
+        back = orc.mse_core_backward if cfg.mode == "mse" else orc.chunk_core_backward
+        run = lambda kc: back(*(ti.to_f64(x[k][0, : kc * cfg.chunk]) for k in ("Z", "Vhat")), W0, cfg.chunk, cfg.eta,
+                              ti.to_f64(x["dO"][0, : kc * cfg.chunk]))
     else:
         x = ti.inplace_inputs(cfg)
         ws = {k: ti.to_f64(x[k]) for k in ("W_gate", "W_up", "W_down0", "W_target", "conv_w")}
@@ -345,7 +352,8 @@ def main():
         if cfg.backward:
             out["config"]["pass"] = "backward of the chunk loop (dZ, dVhat, dW_down0 from dLoss/dO)"
             out["config"]["states"] = "kept by the forward call" if cfg.kept_states else "recomputed"
-            out["metric"] = "TTT chunk-loop backward tokens/s at 128K ctx; % of bf16 MFMA peak"
+            out["metric"] = ("TTT chunk-loop backward tokens/s at " + ("4x64K" if cfg.mode == "mse" else "128K") +
+                             " ctx; % of bf16 MFMA peak")
         if cfg.layer_backward:
             out["config"]["pass"] = "backward of the whole layer (every input and weight gradient from dLoss/dO)"
             out["config"]["states"] = "kept by the forward call" if cfg.kept_states else "recomputed"
