@@ -388,14 +388,15 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
 
 // ------------------------------------------------------------------ backward of the MSE chunk loop
 
-// Workspace of ttt_core_backward_mse: token-contiguous Z, V^ and dO, the state
+// Workspace of ttt_core_backward_mse: token-contiguous V^ and dO (Z is read as
+// it is), the state
 // each chunk was applied with ([k, B, d, f], chunk-major so that one chunk's
 // states are one block), the forward state and the state gradient (fp32, with
 // bf16 operand copies), and one chunk's two residual buffers [B, d, C].
 struct MsePlan {
   int64_t B, n, d, f, C, k;
   size_t esz;
-  size_t off_Zt, off_Vt, off_Gt, off_St, off_Ws, off_Wsh, off_G, off_Gsh, off_Rt, off_Tt, total;
+  size_t off_Vt, off_Gt, off_St, off_Ws, off_Wsh, off_G, off_Gsh, off_Rt, off_Tt, total;
 };
 
 int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p) {
@@ -416,7 +417,6 @@ int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p) {
     *o = off;
     off += align_up(bytes);
   };
-  take(&p->off_Zt, BN * p->f * e);
   take(&p->off_Vt, BN * p->d * e);
   take(&p->off_Gt, BN * p->d * e);
   take(&p->off_St, (size_t)p->k * B * DF * e);
@@ -440,7 +440,7 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
   if (p.B * p.n == 0) return dev(ttt::launch_zero<float>(dW0, df, s));
   const bool bf = sizeof(T) == 2;
   const T* W0 = (const T*)W0v;
-  T* Zt = (T*)(ws + p.off_Zt);
+  const T* Zt = (const T*)Zv;           // Z [B, n, f] as it is (the kernels' row-major operand forms)
   T* Vt = (T*)(ws + p.off_Vt);
   T* Gt = (T*)(ws + p.off_Gt);
   T* St = (T*)(ws + p.off_St);
@@ -453,13 +453,12 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
   T* Rt = (T*)(ws + p.off_Rt);
   T* Tt = (T*)(ws + p.off_Tt);
   const float a = eta / (float)C;
-  int st = dev(ttt::launch_transpose<T>((const T*)Zv, Zt, B, n, f, 1.0f, 0, s));
-  if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)Vv, Vt, B, n, d, 1.0f, 0, s));
+  int st = dev(ttt::launch_transpose<T>((const T*)Vv, Vt, B, n, d, 1.0f, 0, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)dOv, Gt, B, n, d, 1.0f, 0, s));
   // the forward scan again, keeping the state each chunk is applied with (chunk c >= 1: St[c])
   for (int c = 0; c < k && st == TTT_OK; ++c) {
     st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Ws, Wsh, nullptr, Rt, nullptr, false, B, n, d, f, C, c, eta,
-                                      s));
+                                      s, nullptr, true));
     if (st == TTT_OK && c + 1 < k)
       st = dev(ttt::launch_scale<T>(Wcur, St + (int64_t)(c + 1) * B * df, (int64_t)B * df, 1.0f, s));
   }

@@ -980,8 +980,10 @@ __global__ __launch_bounds__(256) void k_zero(T* __restrict__ p, int64_t n) {
 // copy), Q = the chunk's tokens, read from Zt [B, f, n] as an MN-major operand,
 // K = d_ff.
 // GEN (the MSE loop's backward): Rt = rscale O + vscale V^ instead, and O, if
-// not null, is written scaled by oscale; O may be null in either form.
-template <typename T, bool GEN>
+// not null, is written scaled by oscale; O may be null in either form.  ZNAT:
+// Zt is Z [B, n, f] as it is (a K-major operand) instead of its
+// token-contiguous copy.
+template <typename T, bool GEN, bool ZNAT>
 TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __restrict__ W0,
                                        const T* __restrict__ Wcur, T* __restrict__ O, const T* __restrict__ Vt,
                                        T* __restrict__ Rt, const uint8_t* __restrict__ docs, int n, int d, int f,
@@ -1001,11 +1003,14 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
   rscale *= update_flag(umask, b, n / C_, c);       // a masked chunk's update adds zeros
 
   DmaOp<G::NW, G::BP> op;
-  DmaOpMN<T, G::NW, G::BQ> oq;
+  std::conditional_t<ZNAT, DmaOp<G::NW, G::BQ>, DmaOpMN<T, G::NW, G::BQ>> oq;
   // the state chunk c is applied with: W_down0 (shared) where a document starts, else this row's state copy
   const T* W = doc_start(docs, b, n / C_, c, cont) ? W0 : Wcur + (int64_t)b * d * f;
   op.init(W + (int64_t)i0 * f, nullptr, min(G::BP, d - i0), ldb, (unsigned)ldb);
-  oq.init(Zt + (int64_t)b * f * n + (int64_t)c * C_ + t0, min(G::BQ, C_ - t0), (uint64_t)n * esz<T>(), f);
+  if constexpr (ZNAT)
+    oq.init(Zt + row0 * f, nullptr, min(G::BQ, C_ - t0), ldb, (unsigned)ldb);
+  else
+    oq.init(Zt + (int64_t)b * f * n + (int64_t)c * C_ + t0, min(G::BQ, C_ - t0), (uint64_t)n * esz<T>(), f);
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
@@ -1095,7 +1100,9 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
 // is read and written with non-temporal accesses: it is next used by the
 // following chunk's update, and at long-context sizes it is larger than the
 // caches, which are better kept for the operands and for Wsh (read next).
-template <typename T>
+// ZNAT: Zt is Z [B, n, f] as it is (an MN-major operand: d_ff contiguous, the
+// chunk's tokens as the K rows) instead of its token-contiguous copy.
+template <typename T, bool ZNAT>
 TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __restrict__ Rt, const T* __restrict__ W0,
                                         float* __restrict__ Ws, T* __restrict__ Wsh, const uint8_t* __restrict__ docs,
                                         int n, int d, int f, int C_, int c, bool cont) {
@@ -1110,10 +1117,13 @@ TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __res
   const int j0 = tp * G::BP, i0 = tq * G::BQ;
   const unsigned kbytes = (unsigned)C_ * esz<T>();
 
-  DmaOp<G::NW, G::BP> op;
+  std::conditional_t<ZNAT, DmaOpMN<T, G::NW, G::BP>, DmaOp<G::NW, G::BP>> op;
   DmaOp<G::NW, G::BQ> oq;
-  op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C_, nullptr, min(G::BP, f - j0), (uint64_t)n * esz<T>(),
-          kbytes);
+  if constexpr (ZNAT)
+    op.init(Zt + ((int64_t)b * n + (int64_t)c * C_) * f + j0, min(G::BP, f - j0), (uint64_t)f * esz<T>(), C_);
+  else
+    op.init(Zt + ((int64_t)b * f + j0) * n + (int64_t)c * C_, nullptr, min(G::BP, f - j0), (uint64_t)n * esz<T>(),
+            kbytes);
   oq.init(Rt + ((int64_t)b * d + i0) * C_, nullptr, min(G::BQ, d - i0), (uint64_t)kbytes, kbytes);
   float* ws = Ws + (int64_t)b * d * f;
   typename G::Frag acc[G::NPB][G::NQB];
@@ -1299,19 +1309,19 @@ hipError_t launch_mse_apply_gen(const T* Zt, const T* Vt, const T* W0, const T* 
                                 hipStream_t s) {
   const unsigned g = tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B);
   if (gen)
-    k_mse_apply<T, true><<<g, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, nullptr, n, d, f, Cs, c, rscale, cont,
-                                                nullptr, vscale, oscale);
+    k_mse_apply<T, true, true><<<g, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, nullptr, n, d, f, Cs, c, rscale,
+                                                      cont, nullptr, vscale, oscale);
   else
-    k_mse_apply<T, false><<<g, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, nullptr, n, d, f, Cs, c, rscale, cont,
-                                                 nullptr, 0.f, 1.f);
+    k_mse_apply<T, false, true><<<g, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, nullptr, n, d, f, Cs, c, rscale,
+                                                       cont, nullptr, 0.f, 1.f);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_mse_update(const T* Zt, const T* Rt, const T* W0, float* Ws, T* Wsh, bool cont, int B, int n, int d,
                              int f, int Cs, int c, hipStream_t s) {
-  k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, nullptr, n, d, f,
-                                                                               Cs, c, cont);
+  k_mse_update<T, true><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, nullptr, n,
+                                                                                     d, f, Cs, c, cont);
   return hipGetLastError();
 }
 
@@ -1331,13 +1341,20 @@ hipError_t launch_zero(T* p, int64_t n, hipStream_t s) {
 template <typename T>
 hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
                             T* Rt, const uint8_t* docs, bool cont, int B, int n, int d, int f, int Cs, int c,
-                            float eta, hipStream_t s, const uint8_t* umask) {
-  k_mse_apply<T, false><<<tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(
-      Zt, W0, Wcur, O, Vt, Rt, docs, n, d, f, Cs, c, -eta / (float)Cs, cont, umask, 0.f, 1.f);
+                            float eta, hipStream_t s, const uint8_t* umask, bool znat) {
+  const unsigned ga = tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), gu = tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B);
+  if (znat)
+    k_mse_apply<T, false, true><<<ga, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, docs, n, d, f, Cs, c,
+                                                        -eta / (float)Cs, cont, umask, 0.f, 1.f);
+  else
+    k_mse_apply<T, false, false><<<ga, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, docs, n, d, f, Cs, c,
+                                                         -eta / (float)Cs, cont, umask, 0.f, 1.f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_mse_update<T><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, docs, n, d, f,
-                                                                               Cs, c, cont);
+  if (znat)
+    k_mse_update<T, true><<<gu, Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, docs, n, d, f, Cs, c, cont);
+  else
+    k_mse_update<T, false><<<gu, Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, docs, n, d, f, Cs, c, cont);
   return hipGetLastError();
 }
 
@@ -1394,7 +1411,7 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
   template hipError_t launch_zero<T>(T*, int64_t, hipStream_t);                                                   \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
                                           const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t,  \
-                                          const uint8_t*);                                                        \
+                                          const uint8_t*, bool);                                                  \
   template hipError_t launch_state_copy<T>(const float*, float*, T*, int, int64_t, hipStream_t);
 TTT_INST(float)
 TTT_INST(bf16)

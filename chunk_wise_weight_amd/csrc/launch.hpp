@@ -83,6 +83,7 @@ hipError_t launch_sum_rows(const float* Tot, float* out, int B, int64_t df, hipS
 template <typename T>
 hipError_t launch_dz_chunk(const T* Tt, const T* Rt, const T* W, int64_t wsb, const T* S, int64_t ssb, T* dZ, int B,
                            int n, int d, int f, int C, int c, hipStream_t s);
+// (launch_mse_chunk with znat, and the two below: Zt is Z [B, n, f] as it is.)
 // The MSE apply alone for chunk c: Rt = rscale (O - V^)^T, or with gen
 // rscale O^T + vscale V^T and O (if not null) scaled by oscale; the state is
 // W_down0 at chunk 0 unless cont, else Wcur + b d f.
@@ -116,7 +117,7 @@ hipError_t launch_zero(T* p, int64_t n, hipStream_t s);
 template <typename T>
 hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
                             T* Rt, const uint8_t* docs, bool cont, int B, int n, int d, int f, int C, int c,
-                            float eta, hipStream_t s, const uint8_t* umask = nullptr);
+                            float eta, hipStream_t s, const uint8_t* umask = nullptr, bool znat = false);
 template <typename T>
 hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64_t df, hipStream_t s);
 

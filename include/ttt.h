@@ -243,8 +243,8 @@ int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, cons
                       void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-/* Workspace bytes for ttt_core_backward_mse: about B (k d f + 2 n d + n f)
- * dtype elements plus 2 B d f fp32. */
+/* Workspace bytes for ttt_core_backward_mse: about B (k d f + 2 n d) dtype
+ * elements plus 2 B d f fp32. */
 int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes);
 
 /* Gradients through the MSE chunk loop (ttt_core_apply_update with
