@@ -177,10 +177,16 @@ def bench_generic(cfg, steps, warmup):
         shape = cw.InplaceShape(B, n, d, f, cfg.chunk, 1)
         Ws = None
         if cfg.mode == "mse":
-            nbytes = cw.ttt_core_backward_mse_workspace_bytes(shape, dt)
+            if cfg.kept_states:
+                # the forward MSE scan keeps its states (before the timed region, like the other inputs)
+                Ws = torch.empty(B, n // cfg.chunk, d, f, dtype=dt, device="cuda")
+                cw.ttt_core_apply_update(g["Z"], g["Vhat"], g["W_down0"], cfg.chunk, cfg.eta, "mse", W_states=Ws)
+                torch.cuda.synchronize()
+                torch.cuda.empty_cache()
+            nbytes = cw.ttt_core_backward_mse_workspace_bytes(shape, dt, cfg.kept_states)
             ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
             call = lambda: cw.ttt_core_backward_mse(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta, dZ,
-                                                    dV, dW0, ws)
+                                                    dV, dW0, ws, W_states=Ws)
         elif cfg.kept_states:
             # the forward chunk loop keeps its states (before the timed region, like the other inputs)
             Ws = torch.empty(B, n // cfg.chunk, d, f, dtype=dt, device="cuda")

@@ -61,8 +61,9 @@ _SIGNATURES = {
     "ttt_core_apply_update_ex": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P,
                                       ctypes.POINTER(LayerOptions), _P, _P, _P, _S, _P]),
     "ttt_core_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
-    "ttt_core_backward_mse_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, ctypes.POINTER(_S)]),
-    "ttt_core_backward_mse": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "ttt_core_backward_mse_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
+    "ttt_core_backward_mse": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
+                                   _P]),
     "ttt_layer_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
     "ttt_layer_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 18 + [_S, _P]),
     "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
@@ -308,16 +309,18 @@ def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVh
     return dZ, dVhat, dW_down0
 
 
-def ttt_core_backward_mse_workspace_bytes(shape: InplaceShape, dtype: torch.dtype) -> int:
+def ttt_core_backward_mse_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, saved_states=False) -> int:
     n = ctypes.c_size_t()
-    _check(lib().ttt_core_backward_mse_workspace_bytes(ctypes.byref(shape), _dt(dtype), ctypes.byref(n)),
+    _check(lib().ttt_core_backward_mse_workspace_bytes(ctypes.byref(shape), _dt(dtype), int(bool(saved_states)),
+                                                       ctypes.byref(n)),
            "ttt_core_backward_mse_workspace_bytes")
     return n.value
 
 
 def ttt_core_backward_mse(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVhat=None, dW_down0=None,
-                          workspace=None):
-    """Gradients through the MSE chunk loop given dO = dLoss/dO [B, n, d].
+                          workspace=None, W_states=None):
+    """Gradients through the MSE chunk loop given dO = dLoss/dO [B, n, d], with the per-chunk states W_states
+    [B, n // chunk, d, f] kept by the forward call, or recomputed (None).
     Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
@@ -333,10 +336,13 @@ def ttt_core_backward_mse(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None,
     _need(dZ, "dZ", (B, n, f), dt, dev)
     _need(dVhat, "dVhat", (B, n, d), dt, dev)
     _need(dW_down0, "dW_down0", (d, f), torch.float32, dev)
-    nbytes = ttt_core_backward_mse_workspace_bytes(shape, dt)
+    if W_states is not None:
+        _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
+    nbytes = ttt_core_backward_mse_workspace_bytes(shape, dt, W_states is not None)
     ws = _workspace(nbytes, dev, workspace)
+    sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
     _check(lib().ttt_core_backward_mse(ctypes.byref(shape), _dt(dt), float(eta), _ptr(Z), _ptr(Vhat), _ptr(W_down0),
-                                       _ptr(dO), _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
+                                       _ptr(dO), sp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
                                        _stream(dev)),
            "ttt_core_backward_mse")
     return dZ, dVhat, dW_down0

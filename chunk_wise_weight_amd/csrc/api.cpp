@@ -155,8 +155,12 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
       if (st != TTT_OK) return st;
     }
     for (int c = 0; c < k; ++c) {
-      int st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, p.docs, p.Winit != nullptr, B, n, d, f,
-                                            C, c, eta, s, p.umask));
+      int st = TTT_OK;
+      if (p.states != nullptr)      // the state this chunk's apply reads, kept for a backward pass
+        st = dev(ttt::launch_keep_state<T>(W0, Wcur, (T*)p.states, p.docs, p.Winit != nullptr, B, k, c, df, s));
+      if (st == TTT_OK)
+        st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, p.docs, p.Winit != nullptr, B, n, d, f, C,
+                                          c, eta, s, p.umask));
       if (st != TTT_OK) return st;
     }
     return TTT_OK;
@@ -202,7 +206,6 @@ int apply_options(Plan& p, int mode, const ttt_layer_options* o, bool producers)
   if ((o->W_init != nullptr && !ok_ptr(o->W_init)) || (producers && o->x0_halo != nullptr && !ok_ptr(o->x0_halo)) ||
       (o->W_states != nullptr && !ok_ptr(o->W_states)))
     return TTT_ERR_ARG;
-  if (o->W_states != nullptr && mode == TTT_MODE_MSE) return TTT_ERR_ARG;
   p.docs = o->doc_starts;
   p.Winit = o->W_init;
   p.states = o->W_states;
@@ -399,7 +402,7 @@ struct MsePlan {
   size_t off_Vt, off_Gt, off_St, off_Ws, off_Wsh, off_G, off_Gsh, off_Rt, off_Tt, total;
 };
 
-int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p) {
+int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p, bool saved = false) {
   int st = check_inplace_shape(s, dtype);
   if (st != TTT_OK) return st;
   *p = MsePlan{};
@@ -419,11 +422,13 @@ int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p) {
   };
   take(&p->off_Vt, BN * p->d * e);
   take(&p->off_Gt, BN * p->d * e);
-  take(&p->off_St, (size_t)p->k * B * DF * e);
-  take(&p->off_Ws, B * DF * 4);
+  if (!saved) {
+    take(&p->off_St, (size_t)p->k * B * DF * e);
+    take(&p->off_Ws, B * DF * 4);
+  }
   take(&p->off_G, B * DF * 4);
   if (dtype == TTT_BF16) {
-    take(&p->off_Wsh, B * DF * e);
+    if (!saved) take(&p->off_Wsh, B * DF * e);
     take(&p->off_Gsh, B * DF * e);
   }
   take(&p->off_Rt, B * p->d * p->C * e);
@@ -434,7 +439,7 @@ int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p) {
 
 template <typename T>
 int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, const void* W0v, const void* dOv,
-                 void* dZv, void* dVv, float* dW0, char* ws, hipStream_t s) {
+                 const void* Wsaved, void* dZv, void* dVv, float* dW0, char* ws, hipStream_t s) {
   const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
   const int64_t df = (int64_t)d * f;
   if (p.B * p.n == 0) return dev(ttt::launch_zero<float>(dW0, df, s));
@@ -455,8 +460,9 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
   const float a = eta / (float)C;
   int st = dev(ttt::launch_transpose<T>((const T*)Vv, Vt, B, n, d, 1.0f, 0, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)dOv, Gt, B, n, d, 1.0f, 0, s));
-  // the forward scan again, keeping the state each chunk is applied with (chunk c >= 1: St[c])
-  for (int c = 0; c < k && st == TTT_OK; ++c) {
+  // the forward scan again, keeping the state each chunk is applied with (chunk c >= 1: St[c]), unless the
+  // forward call kept them (Wsaved [B, k, d, f], slot c the state chunk c was applied with)
+  for (int c = 0; c < k && st == TTT_OK && Wsaved == nullptr; ++c) {
     st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Ws, Wsh, nullptr, Rt, nullptr, false, B, n, d, f, C, c, eta,
                                       s, nullptr, true));
     if (st == TTT_OK && c + 1 < k)
@@ -465,19 +471,22 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
   // the state gradient G = dLoss/dW_{c+1}, zero after the last chunk, taken back chunk by chunk
   if (st == TTT_OK) st = dev(ttt::launch_zero<float>(G, (int64_t)B * df, s));
   if (st == TTT_OK && bf) st = dev(ttt::launch_zero<T>(Gsh, (int64_t)B * df, s));
+  const bool kept = Wsaved != nullptr;
   for (int c = k - 1; c >= 0 && st == TTT_OK; --c) {
-    const T* Wc = St + (int64_t)c * B * df;                 // read for c >= 1; chunk 0 takes W_down0
+    // W_c of row b: the kept slot (row stride k d f), or the recomputed one (chunk-major; chunk 0 takes W_down0)
+    const T* Wc = kept ? (const T*)Wsaved + (int64_t)c * df : St + (int64_t)c * B * df;
+    const int64_t wstride = kept ? (int64_t)k * df : df;
     // Rt = -(eta/C) R_c^T, R_c = Z_c W_c^T - V^_c
-    st = dev(ttt::launch_mse_apply_gen<T>(Zt, Vt, W0, Wc, nullptr, Rt, false, B, n, d, f, C, c, -a, 0.f, 1.f, false,
-                                          s));
+    st = dev(ttt::launch_mse_apply_gen<T>(Zt, Vt, W0, Wc, nullptr, Rt, kept, B, n, d, f, C, c, -a, 0.f, 1.f, false,
+                                          s, wstride));
     // Tt = T_c^T = (dO_c - (eta/C) Z_c G^T)^T, and dV^_c = (eta/C) Z_c G^T
     if (st == TTT_OK)
       st = dev(ttt::launch_mse_apply_gen<T>(Zt, Gt, W0, Gop, (T*)dVv, Tt, true, B, n, d, f, C, c, -a, 1.0f, a, true,
                                             s));
     // dZ_c = T_c W_c - (eta/C) R_c G
     if (st == TTT_OK)
-      st = dev(ttt::launch_dz_chunk<T>(Tt, Rt, c == 0 ? W0 : Wc, c == 0 ? 0 : df, Gop, df, (T*)dZv, B, n, d, f, C, c,
-                                       s));
+      st = dev(ttt::launch_dz_chunk<T>(Tt, Rt, c == 0 && !kept ? W0 : Wc, c == 0 && !kept ? 0 : wstride, Gop, df,
+                                       (T*)dZv, B, n, d, f, C, c, s));
     // G <- G + T_c^T Z_c = dLoss/dW_c
     if (st == TTT_OK) st = dev(ttt::launch_mse_update<T>(Zt, Tt, W0, G, Gsh, true, B, n, d, f, C, c, s));
   }
@@ -743,22 +752,23 @@ int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, cons
   return core_backward<float>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
 }
 
-int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes) {
+int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states,
+                                          size_t* bytes) {
   if (bytes == nullptr) return TTT_ERR_ARG;
   MsePlan p;
-  int st = make_mse_plan(shape, dtype, &p);
+  int st = make_mse_plan(shape, dtype, &p, saved_states != 0);
   if (st != TTT_OK) return st;
   *bytes = p.total;
   return TTT_OK;
 }
 
 int ttt_core_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
-                          const void* W_down0, const void* dO, void* dZ, void* dVhat, float* dW_down0,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          const void* W_down0, const void* dO, const void* W_states, void* dZ, void* dVhat,
+                          float* dW_down0, void* workspace, size_t workspace_bytes, void* stream) {
   MsePlan p;
-  int st = make_mse_plan(shape, dtype, &p);
+  int st = make_mse_plan(shape, dtype, &p, W_states != nullptr);
   if (st != TTT_OK) return st;
-  if (!finite(eta) || !ok_ptr(dW_down0)) return TTT_ERR_ARG;
+  if (!finite(eta) || !ok_ptr(dW_down0) || (W_states != nullptr && !aligned16(W_states))) return TTT_ERR_ARG;
   if (p.B * p.n > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(W_down0) || !ok_ptr(dO) || !ok_ptr(dZ) ||
                         !ok_ptr(dVhat)))
     return TTT_ERR_ARG;
@@ -766,8 +776,8 @@ int ttt_core_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, 
     return TTT_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == TTT_BF16)
-    return mse_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, dZ, dVhat, dW_down0, (char*)workspace, s);
-  return mse_backward<float>(p, eta, Z, Vhat, W_down0, dO, dZ, dVhat, dW_down0, (char*)workspace, s);
+    return mse_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
+  return mse_backward<float>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
 }
 
 int ttt_layer_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states, size_t* bytes) {

@@ -954,6 +954,21 @@ __global__ __launch_bounds__(256) void k_rev_docs(const uint8_t* __restrict__ do
   rd[e] = t == 0 ? 1 : (docs[b * k + (k - t)] != 0 ? 1 : 0);
 }
 
+// The state the MSE apply of chunk c reads, kept for a backward pass:
+// Ws[b, c] = W_down0 where a document starts (doc_start), else Wcur[b];
+// Ws [B, k, d, f], four elements per thread, grid.y = B.
+template <typename T>
+__global__ __launch_bounds__(256) void k_keep_state(const T* __restrict__ W0, const T* __restrict__ Wcur,
+                                                    T* __restrict__ Ws, const uint8_t* __restrict__ docs, bool cont,
+                                                    int k, int c, int64_t df) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= df) return;
+  const int b = blockIdx.y;
+  const T* src = doc_start(docs, b, k, c, cont) ? W0 : Wcur + (int64_t)b * df;
+  const f32x4 v = load4(src + e);
+  store4(Ws + ((int64_t)b * k + c) * df + e, v[0], v[1], v[2], v[3]);
+}
+
 // dst = scale * src over n elements, four per thread (n % 4 == 0).
 template <typename T>
 __global__ __launch_bounds__(256) void k_scale(const T* __restrict__ src, T* __restrict__ dst, int64_t n,
@@ -988,7 +1003,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
                                        const T* __restrict__ Wcur, T* __restrict__ O, const T* __restrict__ Vt,
                                        T* __restrict__ Rt, const uint8_t* __restrict__ docs, int n, int d, int f,
                                        int C_, int c, float rscale, bool cont, const uint8_t* __restrict__ umask,
-                                       float vscale, float oscale) {
+                                       float vscale, float oscale, int64_t wstride) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
@@ -1005,7 +1020,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
   DmaOp<G::NW, G::BP> op;
   std::conditional_t<ZNAT, DmaOp<G::NW, G::BQ>, DmaOpMN<T, G::NW, G::BQ>> oq;
   // the state chunk c is applied with: W_down0 (shared) where a document starts, else this row's state copy
-  const T* W = doc_start(docs, b, n / C_, c, cont) ? W0 : Wcur + (int64_t)b * d * f;
+  const T* W = doc_start(docs, b, n / C_, c, cont) ? W0 : Wcur + (int64_t)b * wstride;
   op.init(W + (int64_t)i0 * f, nullptr, min(G::BP, d - i0), ldb, (unsigned)ldb);
   if constexpr (ZNAT)
     oq.init(Zt + row0 * f, nullptr, min(G::BQ, C_ - t0), ldb, (unsigned)ldb);
@@ -1306,14 +1321,23 @@ hipError_t launch_dz_chunk(const T* Tt, const T* Rt, const T* W, int64_t wsb, co
 template <typename T>
 hipError_t launch_mse_apply_gen(const T* Zt, const T* Vt, const T* W0, const T* Wcur, T* O, T* Rt, bool cont, int B,
                                 int n, int d, int f, int Cs, int c, float rscale, float vscale, float oscale, bool gen,
-                                hipStream_t s) {
+                                hipStream_t s, int64_t wstride) {
   const unsigned g = tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B);
+  const int64_t df = (int64_t)d * f;
   if (gen)
     k_mse_apply<T, true, true><<<g, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, nullptr, n, d, f, Cs, c, rscale,
-                                                      cont, nullptr, vscale, oscale);
+                                                      cont, nullptr, vscale, oscale, wstride > 0 ? wstride : df);
   else
     k_mse_apply<T, false, true><<<g, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, nullptr, n, d, f, Cs, c, rscale,
-                                                       cont, nullptr, 0.f, 1.f);
+                                                       cont, nullptr, 0.f, 1.f, wstride > 0 ? wstride : df);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_keep_state(const T* W0, const T* Wcur, T* Ws, const uint8_t* docs, bool cont, int B, int k, int c,
+                             int64_t df, hipStream_t s) {
+  if (B == 0 || df == 0) return hipSuccess;
+  k_keep_state<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(W0, Wcur, Ws, docs, cont, k, c, df);
   return hipGetLastError();
 }
 
@@ -1345,10 +1369,10 @@ hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur
   const unsigned ga = tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B), gu = tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B);
   if (znat)
     k_mse_apply<T, false, true><<<ga, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, docs, n, d, f, Cs, c,
-                                                        -eta / (float)Cs, cont, umask, 0.f, 1.f);
+                                                        -eta / (float)Cs, cont, umask, 0.f, 1.f, (int64_t)d * f);
   else
     k_mse_apply<T, false, false><<<ga, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, docs, n, d, f, Cs, c,
-                                                         -eta / (float)Cs, cont, umask, 0.f, 1.f);
+                                                         -eta / (float)Cs, cont, umask, 0.f, 1.f, (int64_t)d * f);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (znat)
@@ -1401,7 +1425,9 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
   template hipError_t launch_dz_chunk<T>(const T*, const T*, const T*, int64_t, const T*, int64_t, T*, int, int,  \
                                          int, int, int, int, hipStream_t);                                        \
   template hipError_t launch_mse_apply_gen<T>(const T*, const T*, const T*, const T*, T*, T*, bool, int, int, int, \
-                                              int, int, int, float, float, float, bool, hipStream_t);             \
+                                              int, int, int, float, float, float, bool, hipStream_t, int64_t);    \
+  template hipError_t launch_keep_state<T>(const T*, const T*, T*, const uint8_t*, bool, int, int, int, int64_t,  \
+                                           hipStream_t);                                                          \
   template hipError_t launch_mse_update<T>(const T*, const T*, const T*, float*, T*, bool, int, int, int, int, int, \
                                            int, hipStream_t);                                                     \
   template hipError_t launch_produce_z_bwd<T>(const T*, const T*, const T*, const T*, T*, int64_t, int, int, int,  \

@@ -87,10 +87,16 @@ hipError_t launch_dz_chunk(const T* Tt, const T* Rt, const T* W, int64_t wsb, co
 // The MSE apply alone for chunk c: Rt = rscale (O - V^)^T, or with gen
 // rscale O^T + vscale V^T and O (if not null) scaled by oscale; the state is
 // W_down0 at chunk 0 unless cont, else Wcur + b d f.
+// Row b's state is Wcur + b wstride (0: d f).
 template <typename T>
 hipError_t launch_mse_apply_gen(const T* Zt, const T* Vt, const T* W0, const T* Wcur, T* O, T* Rt, bool cont, int B,
                                 int n, int d, int f, int C, int c, float rscale, float vscale, float oscale, bool gen,
-                                hipStream_t s);
+                                hipStream_t s, int64_t wstride = 0);
+// Ws [B, k, d, f]: slot c gets the state the MSE apply of chunk c reads (W_down0
+// where a document starts, else Wcur [B, d, f]).
+template <typename T>
+hipError_t launch_keep_state(const T* W0, const T* Wcur, T* Ws, const uint8_t* docs, bool cont, int B, int k, int c,
+                             int64_t df, hipStream_t s);
 // The MSE update alone: Ws (and Wsh) = Ws + Rt Z_c, seeded from W_down0 at chunk 0 unless cont.
 template <typename T>
 hipError_t launch_mse_update(const T* Zt, const T* Rt, const T* W0, float* Ws, T* Wsh, bool cont, int B, int n, int d,

@@ -160,12 +160,13 @@ typedef struct {
    * results up to rounding order. */
   const float* W_init;
   const void* x0_halo;
-  /* Keeping the states for a backward pass (dot objective: TTT_MODE_DOT or
-   * TTT_MODE_DOT_SCAN): W_states [B, k, d, f] dtype (DEVICE, 16-byte
-   * aligned) receives the state each chunk was applied with, W_states[b, c] =
-   * W_c, in place of the workspace copy the call keeps anyway, so keeping
-   * them costs nothing.  ttt_core_backward takes them to skip recomputing
-   * the states.  NULL: not kept.  With the MSE objective: TTT_ERR_ARG. */
+  /* Keeping the states for a backward pass: W_states [B, k, d, f] dtype
+   * (DEVICE, 16-byte aligned) receives the state each chunk was applied
+   * with, W_states[b, c] = W_c.  Dot objective: in place of the workspace copy
+   * the call keeps anyway, so keeping them costs nothing; ttt_core_backward
+   * takes them.  MSE objective: one copy per chunk (2 B d f dtype bytes of
+   * traffic); ttt_core_backward_mse takes them.  Either backward then skips
+   * recomputing the states.  NULL: not kept. */
   void* W_states;
   /* Strided updates (the block-wise mask of the LaCT review's section on the
    * order of the apply and update operations, read onto this layer):
@@ -243,9 +244,12 @@ int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, cons
                       void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes,
                       void* stream);
 
-/* Workspace bytes for ttt_core_backward_mse: about B (k d f + 2 n d) dtype
- * elements plus 2 B d f fp32. */
-int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, size_t* bytes);
+/* Workspace bytes for ttt_core_backward_mse, with the states given
+ * (saved_states = 1) or recomputed (0): about B (k d f + 2 n d) dtype
+ * elements plus 2 B d f fp32, without the k d f and one B d f fp32 when the
+ * states are given. */
+int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states,
+                                          size_t* bytes);
 
 /* Gradients through the MSE chunk loop (ttt_core_apply_update with
  * TTT_MODE_MSE), for a loss that depends on O alone, given dO = dLoss/dO
@@ -257,16 +261,18 @@ int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dt
  *   dVhat_c = (eta/C) Z_c G^T               [B, n, d] dtype
  *   dLoss/dW_c = G + T_c^T Z_c;  dW_down0 = its sum over the rows at c = 0
  *                                           [d, f] fp32
- * The call first runs the forward scan again and keeps the state each chunk
- * was applied with (bf16 copies with bf16), then the reverse recursion: per
+ * The states W_c are W_states [B, k, d, f] dtype when given (kept by the
+ * forward call through ttt_layer_options.W_states; DEVICE, 16-byte aligned),
+ * else the call first runs the forward scan again and keeps them (bf16 copies
+ * with bf16).  Then the reverse recursion: per
  * chunk the MSE apply twice (for R_c, and for T_c with dVhat_c), the
  * two-contraction dZ kernel, and the MSE update seeded with G.  Rows are
  * single documents (no document starts, resumed state or update mask).
  * seq_len == 0 or batch == 0 gives dW_down0 = 0.  Errors as for every entry
  * point. */
 int ttt_core_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
-                          const void* W_down0, const void* dO, void* dZ, void* dVhat, float* dW_down0,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          const void* W_down0, const void* dO, const void* W_states, void* dZ, void* dVhat,
+                          float* dW_down0, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---- backward of the whole dot layer ---- */
 

@@ -271,16 +271,13 @@ def test_layer_backward_validation():
     assert call(0.1, ins, outs, _fake(), 1 << 40, shape=odd) == cw.TTT_ERR_UNSUPPORTED
 
 
-def test_forward_keeps_states_only_for_the_dot_objective():
+def test_forward_rejects_misaligned_kept_states():
     lib = cw.lib()
     s = cw.InplaceShape(1, 2048, 256, 512, 256, 4)
     out = ctypes.c_size_t(0)
     assert lib.ttt_inplace_workspace_bytes(ctypes.byref(s), cw.TTT_BF16, cw.TTT_MODE_MSE, 0,
                                            ctypes.byref(out)) == cw.TTT_OK
-    opts = cw.LayerOptions(None, 0, None, None, _fake())
     args = [_fake() for _ in range(3)]    # Z, Vhat, W_down0
-    assert lib.ttt_core_apply_update_ex(ctypes.byref(s), cw.TTT_BF16, cw.TTT_MODE_MSE, 0.1, *args, ctypes.byref(opts),
-                                        _fake(), _fake(), _fake(), out.value, None) == cw.TTT_ERR_ARG
     opts = cw.LayerOptions(None, 0, None, None, ctypes.c_void_p(0x100004))
     assert lib.ttt_core_apply_update_ex(ctypes.byref(s), cw.TTT_BF16, cw.TTT_MODE_DOT, 0.1, *args, ctypes.byref(opts),
                                         _fake(), _fake(), _fake(), 1 << 40, None) == cw.TTT_ERR_ARG

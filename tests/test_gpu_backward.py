@@ -158,8 +158,14 @@ def test_layer_keeps_states():
     O1 = cw.ttt_chunk_apply(Zt, Ws, cfg.chunk)          # the kept states reproduce the outputs
     torch.cuda.synchronize()
     assert torch.equal(O, O0) and torch.equal(Wf, Wf0) and torch.equal(O1, O)
-    with pytest.raises(cw.TTTError):
-        cw.ttt_chunk_apply_update(*args[:-1], 0.5, "mse", W_states=Ws)
+    # the MSE scan keeps them too (one copy per chunk): chunk 0 saw W_down0, and they reproduce the outputs
+    Om, Wm = cw.ttt_chunk_apply_update(*args[:-1], 0.5, "mse", W_states=Ws)
+    Om0, Wm0 = cw.ttt_chunk_apply_update(*args[:-1], 0.5, "mse")
+    O2 = cw.ttt_chunk_apply(Zt, Ws, cfg.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(Om, Om0) and torch.equal(Wm, Wm0)
+    assert torch.equal(Ws[:, 0], g["W_down0"].expand(2, 264, 392))
+    assert rel(f64(O2), f64(Om)) < 2e-3
 
 
 def test_full_size_backward_sampled():
@@ -316,3 +322,22 @@ def test_mse_backward_reduced_workload():
     got, ref = mse_run(cfg)
     for name, a, b in zip(("dZ", "dVhat", "dW_down0"), got, ref):
         assert rel(a, b) < TOL["bf16"], name
+
+
+@pytest.mark.parametrize("dtype,C", [("f32", 96), ("bf16", 128)])
+def test_mse_backward_with_kept_states(dtype, C):
+    # the states the MSE forward keeps stand in for the backward's recomputed ones
+    cfg = cfg_of(dtype, 2, 4, C, eta=0.5)
+    x = ti.backward_inputs(cfg)
+    g = {name: t.cuda() for name, t in x.items()}
+    B, d, f = 2, cfg.d_model, cfg.d_ff
+    Ws = torch.full((B, 4, d, f), float("nan"), dtype=g["Z"].dtype, device="cuda")
+    cw.ttt_core_apply_update(g["Z"], g["Vhat"], g["W_down0"], C, cfg.eta, "mse", W_states=Ws)
+    kept = cw.ttt_core_backward_mse(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta, W_states=Ws)
+    again = cw.ttt_core_backward_mse(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dZ", "dVhat", "dW_down0"), kept, again):
+        assert rel(f64(a), f64(b)) < 1e-3, name
+    _, ref = mse_run(cfg)
+    for name, a, b in zip(("dZ", "dVhat", "dW_down0"), kept, ref):
+        assert rel(f64(a), b) < TOL[dtype], name

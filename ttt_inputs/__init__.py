@@ -98,8 +98,9 @@ class InplaceConfig:
         if self.layer_backward:
             return float(self.tokens) * ((24.0 if self.kept_states else 26.0) * d * f + 6.0 * d * d)
         if self.backward and self.mode == "mse":
-            # the forward scan again (4df), then per chunk two applies, dZ's two contractions and the update
-            return float(self.tokens) * 14.0 * d * f
+            # the forward scan again (4df, unless the states are kept), then per chunk two applies, dZ's two
+            # contractions and the update
+            return float(self.tokens) * (10.0 if self.kept_states else 14.0) * d * f
         if self.backward:
             return float(self.tokens) * (8.0 if self.kept_states else 10.0) * d * f
         return float(self.tokens) * (8.0 * d * f + 2.0 * d * d + 2.0 * K * d)
@@ -193,6 +194,8 @@ WORKLOADS = {
     # the backward of the MSE chunk loop at the MSE workload's shape
     "mse_bwd_bf16_4x64k": InplaceConfig("mse_bwd_bf16_4x64k", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16", seed=1006,
                                         backward=True),
+    "mse_bwd_bf16_4x64k_kept": InplaceConfig("mse_bwd_bf16_4x64k_kept", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16",
+                                             seed=1006, backward=True, kept_states=True),
     "mse_bf16_4x64k": InplaceConfig("mse_bf16_4x64k", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16", seed=1003),
     "lact_bf16_256k": LactConfig("lact_bf16_256k", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004),
     # the LaCT review's own update: dot-product loss, per-token learning rates, L2 weight normalisation
