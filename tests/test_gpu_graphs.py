@@ -1,7 +1,8 @@
 """The layer calls captured into HIP graphs (torch.cuda.CUDAGraph drives the capture).
 
 The library enqueues kernels only -- no allocation, copy or memset -- and the LaCT call adds an event fork and
-join with a side stream, which a capture records as parallel branches.  Each graph is replayed three times with
+join with a side stream, which a capture records as parallel branches.  The backward entry points (the dot and MSE
+chunk loops, the whole dot layer) are captured the same way.  Each graph is replayed three times with
 the outputs clobbered, eager calls and synchronisations in between, and every replay must reproduce the eager
 call's bits.
 """
@@ -30,9 +31,21 @@ def _lact():
     return lambda: cw.ttt_lact_swiglu(*args)
 
 
-@pytest.mark.parametrize("kind", ["dot", "mse", "lact"])
+def _backward(kind):
+    cfg = ti.InplaceConfig("graph", 2, 512, 264, 392, 128, 0.05 if kind != "mse_backward" else 0.5,
+                           "mse" if kind == "mse_backward" else "dot", "bf16", seed=19, backward=True)
+    g = {k: v.cuda() for k, v in ti.backward_inputs(cfg).items()}
+    if kind == "layer_backward":
+        x = {k: v.cuda() for k, v in ti.inplace_inputs(cfg.with_(backward=False)).items()}
+        args = (x["H"], x["X0"], x["W_gate"], x["W_up"], x["W_down0"], x["W_target"], x["conv_w"], g["dO"])
+        return lambda: cw.ttt_layer_backward(*args, cfg.chunk, cfg.eta)
+    fn = cw.ttt_core_backward_mse if kind == "mse_backward" else cw.ttt_core_backward
+    return lambda: fn(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta)
+
+
+@pytest.mark.parametrize("kind", ["dot", "mse", "lact", "backward", "mse_backward", "layer_backward"])
 def test_graph_replays_match_eager(kind):
-    call = _lact() if kind == "lact" else _inplace(kind)
+    call = _lact() if kind == "lact" else _backward(kind) if "backward" in kind else _inplace(kind)
     eager = call()
     torch.cuda.synchronize()
     # warm-up on a side stream, as torch asks before a capture
