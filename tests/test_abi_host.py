@@ -271,6 +271,40 @@ def test_layer_backward_validation():
     assert call(0.1, ins, outs, _fake(), 1 << 40, shape=odd) == cw.TTT_ERR_UNSUPPORTED
 
 
+def test_mse_backward_validation():
+    """ttt_core_backward_mse: workspace sizes with and without kept states, and validation before device work."""
+    lib = cw.lib()
+    al = lambda x: (x + 255) // 256 * 256
+    B, n, d, f, C = 2, 1024, 256, 512, 256
+    k, e = n // C, 2
+    s = cw.InplaceShape(B, n, d, f, C, 1)
+
+    def ws(saved):
+        out = ctypes.c_size_t(0)
+        assert lib.ttt_core_backward_mse_workspace_bytes(ctypes.byref(s), cw.TTT_BF16, saved,
+                                                         ctypes.byref(out)) == cw.TTT_OK
+        return out.value
+
+    # V^ and dO token-contiguous, the state gradient (fp32 + bf16 copy), two chunk residual buffers; the recomputing
+    # call adds the chunk-major states, the forward state and its bf16 copy
+    common = 2 * al(B * n * d * e) + al(B * d * f * 4) + al(B * d * f * e) + 2 * al(B * d * C * e)
+    assert ws(1) == common
+    assert ws(0) == common + al(k * B * d * f * e) + al(B * d * f * 4) + al(B * d * f * e)
+    ins = [_fake() for _ in range(4)]      # Z, Vhat, W_down0, dO
+    outs = [_fake() for _ in range(2)]     # dZ, dVhat
+
+    def call(eta, ins, Ws, dW, w, nbytes):
+        return lib.ttt_core_backward_mse(ctypes.byref(s), cw.TTT_BF16, eta, *ins, Ws, *outs, dW, w, nbytes, None)
+
+    nb = ws(0)
+    assert call(0.1, ins, None, _fake(), _fake(), nb - 1) == cw.TTT_ERR_WORKSPACE
+    assert call(0.1, ins, _fake(), _fake(), _fake(), ws(1) - 1) == cw.TTT_ERR_WORKSPACE
+    assert call(float("nan"), ins, None, _fake(), _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, ins, None, None, _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, [ctypes.c_void_p(0x100002)] + ins[1:], None, _fake(), _fake(), nb) == cw.TTT_ERR_ARG
+    assert call(0.1, ins, ctypes.c_void_p(0x100004), _fake(), _fake(), nb) == cw.TTT_ERR_ARG
+
+
 def test_forward_rejects_misaligned_kept_states():
     lib = cw.lib()
     s = cw.InplaceShape(1, 2048, 256, 512, 256, 4)
