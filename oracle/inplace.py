@@ -214,7 +214,7 @@ def chunk_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None):
     return dZ, dV, dW0
 
 
-def mse_core_backward(Z, Vhat, W0, chunk, eta, dO):
+def mse_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None):
     """Gradients of a loss through the MSE chunk loop (chunk_apply_update with
     mode "mse"), given dO = dLoss/dO: returns (dZ [n, f], dVhat [n, d],
     dW0 [d, f]).  Per chunk (eq. (3)-(4)): O_c = Z_c W_c^T, R_c = Z_c W_c^T -
@@ -224,7 +224,15 @@ def mse_core_backward(Z, Vhat, W0, chunk, eta, dO):
       dZ_c     = T_c W_c - (eta/C) R_c G
       dVhat_c  = (eta/C) Z_c G^T
       dLoss/dW_c = G + T_c^T Z_c,
-    and dW0 is dLoss/dW_0.  The loss is taken to depend on O only."""
+    and dW0 is dLoss/dW_0.  The loss is taken to depend on O only.
+    `doc_starts` [n_chunks] packs documents as in inplace_layer; they are
+    independent sequences, so the gradients are those of each document taken
+    alone, dW0 summed over them."""
+    if doc_starts is not None:
+        cuts = [c * chunk for c in range(len(doc_starts)) if c == 0 or doc_starts[c]] + [len(Z)]
+        parts = [mse_core_backward(Z[a:e], Vhat[a:e], W0, chunk, eta, dO[a:e]) for a, e in zip(cuts[:-1], cuts[1:])]
+        return (np.concatenate([q[0] for q in parts]), np.concatenate([q[1] for q in parts]),
+                sum(q[2] for q in parts))
     Z, Vhat, W0, dO = _f64(Z), _f64(Vhat), _f64(W0), _f64(dO)
     n = Z.shape[0]
     bounds = [(s, min(s + chunk, n)) for s in range(0, n, chunk)]

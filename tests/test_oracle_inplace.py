@@ -756,3 +756,25 @@ def test_mse_core_backward_matches_autograd(n, C):
     np.testing.assert_allclose(dW0, grad(tw), rtol=1e-11, atol=1e-11)
     np.testing.assert_allclose(_torch_mse_chunk_loop(tz, tv, tw, C, eta).detach().numpy(),
                                orc.chunk_apply_update(Z, V, W0, C, eta, "mse")[0], rtol=1e-12, atol=1e-12)
+
+
+def test_mse_core_backward_with_documents_matches_autograd():
+    """Packed documents in the MSE loop: autograd of the loop restarting from W0 at every flagged chunk."""
+    rng = _rng(57)
+    n, C, d, f, eta = 15, 3, 3, 4, 0.4
+    starts = np.array([1, 0, 1, 1, 0])
+    Z, V, W0, dO = (rng.standard_normal(s) for s in ((n, f), (n, d), (d, f), (n, d)))
+    dZ, dV, dW0 = orc.mse_core_backward(Z, V, W0, C, eta, dO, doc_starts=starts)
+    tz, tv, tw = (torch.tensor(a, requires_grad=True) for a in (Z, V, W0))
+    W, outs = tw, []
+    for c, s in enumerate(range(0, n, C)):
+        if starts[c]:
+            W = tw
+        Zc, Vc = tz[s:s + C], tv[s:s + C]
+        O = Zc @ W.T
+        outs.append(O)
+        W = W - (eta / C) * ((O - Vc).T @ Zc)
+    (torch.cat(outs) * torch.from_numpy(dO)).sum().backward()
+    np.testing.assert_allclose(dZ, tz.grad.numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dV, tv.grad.numpy(), rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(dW0, tw.grad.numpy(), rtol=1e-11, atol=1e-11)
