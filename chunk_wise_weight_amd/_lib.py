@@ -62,8 +62,8 @@ _SIGNATURES = {
                                       ctypes.POINTER(LayerOptions), _P, _P, _P, _S, _P]),
     "ttt_core_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
     "ttt_core_backward_mse_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
-    "ttt_core_backward_mse": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
-                                   _P]),
+    "ttt_core_backward_mse": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   _S, _P]),
     "ttt_layer_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
     "ttt_layer_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 18 + [_S, _P]),
     "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
@@ -234,10 +234,10 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
 
 
 def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", O=None, W_final=None,
-                          workspace=None, W_states=None, update_mask=None):
+                          workspace=None, W_states=None, update_mask=None, doc_starts=None):
     """The chunk loop given Z [B, n, f] and Vhat [B, n, d].  Returns (O, W_final).  W_states [B, n // chunk, d, f]
-    (dtype), if given, receives the per-chunk states of the dot objective; update_mask [B, n // chunk] as for the
-    layer (both through ttt_core_apply_update_ex)."""
+    (dtype), if given, receives the per-chunk states; update_mask and doc_starts [B, n // chunk] as for the layer
+    (all through ttt_core_apply_update_ex)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
     dt, dev = Z.dtype, Z.device
@@ -252,11 +252,12 @@ def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", 
     nbytes = ttt_inplace_workspace_bytes(shape, dt, mode, False)
     ws = _workspace(nbytes, dev, workspace)
     update_mask = _flags(update_mask, "update_mask", (B, n // chunk if chunk > 0 else 0), dev)
-    if W_states is not None or update_mask is not None:
+    doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
+    if W_states is not None or update_mask is not None or doc_starts is not None:
         if W_states is not None:
             _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
         ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
-        opts = LayerOptions(None, 0, None, None, ptr(W_states), ptr(update_mask))
+        opts = LayerOptions(ptr(doc_starts), 0, None, None, ptr(W_states), ptr(update_mask))
         _check(lib().ttt_core_apply_update_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(Z),
                                               _ptr(Vhat), _ptr(W_down0), ctypes.byref(opts), _ptr(O), _ptr(W_final),
                                               _ptr(ws), nbytes, _stream(dev)),
@@ -318,9 +319,10 @@ def ttt_core_backward_mse_workspace_bytes(shape: InplaceShape, dtype: torch.dtyp
 
 
 def ttt_core_backward_mse(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVhat=None, dW_down0=None,
-                          workspace=None, W_states=None):
+                          workspace=None, W_states=None, doc_starts=None):
     """Gradients through the MSE chunk loop given dO = dLoss/dO [B, n, d], with the per-chunk states W_states
-    [B, n // chunk, d, f] kept by the forward call, or recomputed (None).
+    [B, n // chunk, d, f] kept by the forward call, or recomputed (None); doc_starts [B, n // chunk] packs documents
+    as for the forward layer.
     Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
@@ -341,8 +343,10 @@ def ttt_core_backward_mse(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None,
     nbytes = ttt_core_backward_mse_workspace_bytes(shape, dt, W_states is not None)
     ws = _workspace(nbytes, dev, workspace)
     sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
+    doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
+    dp = ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None and doc_starts.numel() else None
     _check(lib().ttt_core_backward_mse(ctypes.byref(shape), _dt(dt), float(eta), _ptr(Z), _ptr(Vhat), _ptr(W_down0),
-                                       _ptr(dO), sp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
+                                       _ptr(dO), sp, dp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
                                        _stream(dev)),
            "ttt_core_backward_mse")
     return dZ, dVhat, dW_down0

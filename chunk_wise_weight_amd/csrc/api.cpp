@@ -399,7 +399,8 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
 struct MsePlan {
   int64_t B, n, d, f, C, k;
   size_t esz;
-  size_t off_Vt, off_Gt, off_St, off_Ws, off_Wsh, off_G, off_Gsh, off_Rt, off_Tt, total;
+  const uint8_t* docs;  // document starts [B, k] (device) or null
+  size_t off_Vt, off_Gt, off_St, off_Ws, off_Wsh, off_G, off_Gsh, off_Rt, off_Tt, off_acc, total;
 };
 
 int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p, bool saved = false) {
@@ -433,6 +434,7 @@ int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p, bool saved 
   }
   take(&p->off_Rt, B * p->d * p->C * e);
   take(&p->off_Tt, B * p->d * p->C * e);
+  take(&p->off_acc, B * DF * 4);           // per-row sums of dW_down0 over documents (packed rows)
   p->total = off;
   return TTT_OK;
 }
@@ -460,24 +462,25 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
   const float a = eta / (float)C;
   int st = dev(ttt::launch_transpose<T>((const T*)Vv, Vt, B, n, d, 1.0f, 0, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)dOv, Gt, B, n, d, 1.0f, 0, s));
-  // the forward scan again, keeping the state each chunk is applied with (chunk c >= 1: St[c]), unless the
-  // forward call kept them (Wsaved [B, k, d, f], slot c the state chunk c was applied with)
+  // the forward scan again, keeping in St [B, k, d, f] the state each chunk's apply reads (W_down0 at a document
+  // start), unless the forward call kept them the same way (Wsaved)
   for (int c = 0; c < k && st == TTT_OK && Wsaved == nullptr; ++c) {
-    st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Ws, Wsh, nullptr, Rt, nullptr, false, B, n, d, f, C, c, eta,
-                                      s, nullptr, true));
-    if (st == TTT_OK && c + 1 < k)
-      st = dev(ttt::launch_scale<T>(Wcur, St + (int64_t)(c + 1) * B * df, (int64_t)B * df, 1.0f, s));
+    st = dev(ttt::launch_keep_state<T>(W0, Wcur, St, p.docs, false, B, k, c, df, s));
+    if (st == TTT_OK)
+      st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Ws, Wsh, nullptr, Rt, p.docs, false, B, n, d, f, C, c, eta,
+                                        s, nullptr, true));
   }
   // the state gradient G = dLoss/dW_{c+1}, zero after the last chunk, taken back chunk by chunk
   if (st == TTT_OK) st = dev(ttt::launch_zero<float>(G, (int64_t)B * df, s));
   if (st == TTT_OK && bf) st = dev(ttt::launch_zero<T>(Gsh, (int64_t)B * df, s));
-  const bool kept = Wsaved != nullptr;
+  float* acc = (float*)(ws + p.off_acc);
+  if (st == TTT_OK && p.docs != nullptr) st = dev(ttt::launch_zero<float>(acc, (int64_t)B * df, s));
+  const T* Sb = Wsaved != nullptr ? (const T*)Wsaved : (const T*)St;
+  const int64_t wstride = (int64_t)k * df;
   for (int c = k - 1; c >= 0 && st == TTT_OK; --c) {
-    // W_c of row b: the kept slot (row stride k d f), or the recomputed one (chunk-major; chunk 0 takes W_down0)
-    const T* Wc = kept ? (const T*)Wsaved + (int64_t)c * df : St + (int64_t)c * B * df;
-    const int64_t wstride = kept ? (int64_t)k * df : df;
+    const T* Wc = Sb + (int64_t)c * df;                     // row b's W_c at Wc + b k d f
     // Rt = -(eta/C) R_c^T, R_c = Z_c W_c^T - V^_c
-    st = dev(ttt::launch_mse_apply_gen<T>(Zt, Vt, W0, Wc, nullptr, Rt, kept, B, n, d, f, C, c, -a, 0.f, 1.f, false,
+    st = dev(ttt::launch_mse_apply_gen<T>(Zt, Vt, W0, Wc, nullptr, Rt, true, B, n, d, f, C, c, -a, 0.f, 1.f, false,
                                           s, wstride));
     // Tt = T_c^T = (dO_c - (eta/C) Z_c G^T)^T, and dV^_c = (eta/C) Z_c G^T
     if (st == TTT_OK)
@@ -485,12 +488,14 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
                                             s));
     // dZ_c = T_c W_c - (eta/C) R_c G
     if (st == TTT_OK)
-      st = dev(ttt::launch_dz_chunk<T>(Tt, Rt, c == 0 && !kept ? W0 : Wc, c == 0 && !kept ? 0 : wstride, Gop, df,
-                                       (T*)dZv, B, n, d, f, C, c, s));
+      st = dev(ttt::launch_dz_chunk<T>(Tt, Rt, Wc, wstride, Gop, df, (T*)dZv, B, n, d, f, C, c, s));
     // G <- G + T_c^T Z_c = dLoss/dW_c
     if (st == TTT_OK) st = dev(ttt::launch_mse_update<T>(Zt, Tt, W0, G, Gsh, true, B, n, d, f, C, c, s));
+    // packed rows: a document's first chunk hands its gradient to dW_down0, and the one before starts from zero
+    if (st == TTT_OK && p.docs != nullptr)
+      st = dev(ttt::launch_doc_grad_reset<T>(G, Gsh, acc, p.docs, B, k, c, df, s));
   }
-  if (st == TTT_OK) st = dev(ttt::launch_sum_rows(G, dW0, B, df, s));
+  if (st == TTT_OK) st = dev(ttt::launch_sum_rows(p.docs != nullptr ? acc : G, dW0, B, df, s));
   return st;
 }
 
@@ -763,11 +768,13 @@ int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dt
 }
 
 int ttt_core_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
-                          const void* W_down0, const void* dO, const void* W_states, void* dZ, void* dVhat,
-                          float* dW_down0, void* workspace, size_t workspace_bytes, void* stream) {
+                          const void* W_down0, const void* dO, const void* W_states, const unsigned char* doc_starts,
+                          void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes,
+                          void* stream) {
   MsePlan p;
   int st = make_mse_plan(shape, dtype, &p, W_states != nullptr);
   if (st != TTT_OK) return st;
+  p.docs = doc_starts;
   if (!finite(eta) || !ok_ptr(dW_down0) || (W_states != nullptr && !aligned16(W_states))) return TTT_ERR_ARG;
   if (p.B * p.n > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(W_down0) || !ok_ptr(dO) || !ok_ptr(dZ) ||
                         !ok_ptr(dVhat)))

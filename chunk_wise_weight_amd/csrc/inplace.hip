@@ -969,6 +969,24 @@ __global__ __launch_bounds__(256) void k_keep_state(const T* __restrict__ W0, co
   store4(Ws + ((int64_t)b * k + c) * df + e, v[0], v[1], v[2], v[3]);
 }
 
+// The MSE backward at a document start (packed rows): chunk c of row b starts
+// a document, so the state gradient G[b] = dLoss/dW_c is that document's
+// contribution to dW_down0 (acc[b] += G[b]) and the previous document's last
+// chunk receives none (G[b] = 0, and its operand copy Gsh[b] if any).
+template <typename T>
+__global__ __launch_bounds__(256) void k_doc_grad_reset(float* __restrict__ G, T* __restrict__ Gsh,
+                                                        float* __restrict__ acc, const uint8_t* __restrict__ docs,
+                                                        int k, int c, int64_t df) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  const int b = blockIdx.y;
+  if (e >= df || !doc_start(docs, b, k, c)) return;
+  const int64_t o = (int64_t)b * df + e;
+  const f32x4 g = load4(G + o), a = load4(acc + o);
+  store4(acc + o, a[0] + g[0], a[1] + g[1], a[2] + g[2], a[3] + g[3]);
+  store4(G + o, 0.f, 0.f, 0.f, 0.f);
+  if (Gsh != nullptr) store4(Gsh + o, 0.f, 0.f, 0.f, 0.f);
+}
+
 // dst = scale * src over n elements, four per thread (n % 4 == 0).
 template <typename T>
 __global__ __launch_bounds__(256) void k_scale(const T* __restrict__ src, T* __restrict__ dst, int64_t n,
@@ -1342,6 +1360,14 @@ hipError_t launch_keep_state(const T* W0, const T* Wcur, T* Ws, const uint8_t* d
 }
 
 template <typename T>
+hipError_t launch_doc_grad_reset(float* G, T* Gsh, float* acc, const uint8_t* docs, int B, int k, int c, int64_t df,
+                                 hipStream_t s) {
+  if (B == 0 || df == 0) return hipSuccess;
+  k_doc_grad_reset<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(G, Gsh, acc, docs, k, c, df);
+  return hipGetLastError();
+}
+
+template <typename T>
 hipError_t launch_mse_update(const T* Zt, const T* Rt, const T* W0, float* Ws, T* Wsh, bool cont, int B, int n, int d,
                              int f, int Cs, int c, hipStream_t s) {
   k_mse_update<T, true><<<tiles_u(cdiv(f, kWB) * cdiv(d, kWB) * B), Wide::NT, 0, s>>>(Zt, Rt, W0, Ws, Wsh, nullptr, n,
@@ -1426,6 +1452,8 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
                                          int, int, int, int, hipStream_t);                                        \
   template hipError_t launch_mse_apply_gen<T>(const T*, const T*, const T*, const T*, T*, T*, bool, int, int, int, \
                                               int, int, int, float, float, float, bool, hipStream_t, int64_t);    \
+  template hipError_t launch_doc_grad_reset<T>(float*, T*, float*, const uint8_t*, int, int, int, int64_t,       \
+                                               hipStream_t);                                                      \
   template hipError_t launch_keep_state<T>(const T*, const T*, T*, const uint8_t*, bool, int, int, int, int64_t,  \
                                            hipStream_t);                                                          \
   template hipError_t launch_mse_update<T>(const T*, const T*, const T*, float*, T*, bool, int, int, int, int, int, \

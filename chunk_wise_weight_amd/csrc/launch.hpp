@@ -92,6 +92,10 @@ template <typename T>
 hipError_t launch_mse_apply_gen(const T* Zt, const T* Vt, const T* W0, const T* Wcur, T* O, T* Rt, bool cont, int B,
                                 int n, int d, int f, int C, int c, float rscale, float vscale, float oscale, bool gen,
                                 hipStream_t s, int64_t wstride = 0);
+// MSE backward, packed rows: where chunk c starts row b's document, acc[b] += G[b] and G[b] (and Gsh[b]) = 0.
+template <typename T>
+hipError_t launch_doc_grad_reset(float* G, T* Gsh, float* acc, const uint8_t* docs, int B, int k, int c, int64_t df,
+                                 hipStream_t s);
 // Ws [B, k, d, f]: slot c gets the state the MSE apply of chunk c reads (W_down0
 // where a document starts, else Wcur [B, d, f]).
 template <typename T>

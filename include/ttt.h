@@ -246,7 +246,7 @@ int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, cons
 
 /* Workspace bytes for ttt_core_backward_mse, with the states given
  * (saved_states = 1) or recomputed (0): about B (k d f + 2 n d) dtype
- * elements plus 2 B d f fp32, without the k d f and one B d f fp32 when the
+ * elements plus 3 B d f fp32, without the k d f and one B d f fp32 when the
  * states are given. */
 int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states,
                                           size_t* bytes);
@@ -266,13 +266,17 @@ int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dt
  * else the call first runs the forward scan again and keeps them (bf16 copies
  * with bf16).  Then the reverse recursion: per
  * chunk the MSE apply twice (for R_c, and for T_c with dVhat_c), the
- * two-contraction dZ kernel, and the MSE update seeded with G.  Rows are
- * single documents (no document starts, resumed state or update mask).
+ * two-contraction dZ kernel, and the MSE update seeded with G.  doc_starts
+ * [B, k] (DEVICE, as ttt_layer_options.doc_starts; NULL: one document per
+ * row) packs documents: at a document's first chunk G goes to dW_down0 and
+ * restarts from zero for the chunk before.  Resumed rows and update masks
+ * are not handled.
  * seq_len == 0 or batch == 0 gives dW_down0 = 0.  Errors as for every entry
  * point. */
 int ttt_core_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
-                          const void* W_down0, const void* dO, const void* W_states, void* dZ, void* dVhat,
-                          float* dW_down0, void* workspace, size_t workspace_bytes, void* stream);
+                          const void* W_down0, const void* dO, const void* W_states, const unsigned char* doc_starts,
+                          void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* ---- backward of the whole dot layer ---- */
 

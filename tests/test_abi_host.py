@@ -287,14 +287,16 @@ def test_mse_backward_validation():
 
     # V^ and dO token-contiguous, the state gradient (fp32 + bf16 copy), two chunk residual buffers; the recomputing
     # call adds the chunk-major states, the forward state and its bf16 copy
-    common = 2 * al(B * n * d * e) + al(B * d * f * 4) + al(B * d * f * e) + 2 * al(B * d * C * e)
+    common = 2 * al(B * n * d * e) + al(B * d * f * 4) + al(B * d * f * e) + 2 * al(B * d * C * e) + \
+        al(B * d * f * 4)     # + the per-row dW_down0 sums of packed rows
     assert ws(1) == common
     assert ws(0) == common + al(k * B * d * f * e) + al(B * d * f * 4) + al(B * d * f * e)
     ins = [_fake() for _ in range(4)]      # Z, Vhat, W_down0, dO
     outs = [_fake() for _ in range(2)]     # dZ, dVhat
 
     def call(eta, ins, Ws, dW, w, nbytes):
-        return lib.ttt_core_backward_mse(ctypes.byref(s), cw.TTT_BF16, eta, *ins, Ws, *outs, dW, w, nbytes, None)
+        return lib.ttt_core_backward_mse(ctypes.byref(s), cw.TTT_BF16, eta, *ins, Ws, None, *outs, dW, w, nbytes,
+                                         None)
 
     nb = ws(0)
     assert call(0.1, ins, None, _fake(), _fake(), nb - 1) == cw.TTT_ERR_WORKSPACE

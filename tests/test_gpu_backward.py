@@ -341,3 +341,28 @@ def test_mse_backward_with_kept_states(dtype, C):
     _, ref = mse_run(cfg)
     for name, a, b in zip(("dZ", "dVhat", "dW_down0"), kept, ref):
         assert rel(f64(a), b) < TOL[dtype], name
+
+
+@pytest.mark.parametrize("dtype,C", [("f32", 96), ("bf16", 128)])
+def test_mse_backward_packed_documents(dtype, C):
+    """Packed documents in the MSE loop's backward (recomputed states, and states kept by the forward call with the
+    same document starts): row 0 starts a document every other chunk, row 1 at every chunk, row 2 holds one."""
+    cfg = cfg_of(dtype, 3, 6, C, eta=0.5)
+    x = ti.backward_inputs(cfg)
+    g = {name: t.cuda() for name, t in x.items()}
+    starts = np.zeros((3, 6), dtype=np.uint8)
+    starts[0, ::2] = 1
+    starts[1, :] = 1
+    dst = torch.from_numpy(starts).cuda()
+    got = cw.ttt_core_backward_mse(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta, doc_starts=dst)
+    Ws = torch.empty(3, 6, cfg.d_model, cfg.d_ff, dtype=g["Z"].dtype, device="cuda")
+    cw.ttt_core_apply_update(g["Z"], g["Vhat"], g["W_down0"], C, cfg.eta, "mse", W_states=Ws, doc_starts=dst)
+    kept = cw.ttt_core_backward_mse(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta, doc_starts=dst, W_states=Ws)
+    torch.cuda.synchronize()
+    Z, V, W0, dO = (ti.to_f64(x[name]) for name in ("Z", "Vhat", "W_down0", "dO"))
+    outs = [orc.mse_core_backward(Z[b], V[b], W0, C, cfg.eta, dO[b], doc_starts=starts[b]) for b in range(3)]
+    ref = (np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]), sum(o[2] for o in outs))
+    for res in (got, kept):
+        for name, a, b in zip(("dZ", "dVhat", "dW_down0"), res, ref):
+            assert rel(f64(a), b) < TOL[dtype], name
+    assert not torch.any(got[1][1])       # a document per chunk: no later state in any document
