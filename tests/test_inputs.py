@@ -45,3 +45,32 @@ def test_workload_flop_counts():
     assert cfg.flops() == 131072 * (8 * d * f + 2 * d * d + 8 * d)
     lc = ti.workload("lact_bf16_256k")
     assert lc.flops() == 262144 * 4 * 20 * 512 * 1024
+
+
+def test_every_workload_states_its_flops():
+    """Every workload's algorithmic flop count per token: the layer (8df + 2d^2 + 2Kd for In-Place, 20 dh m per head
+    for LaCT before its variants), the chunk loop's backward (10df, 8df with kept states; 14df and 10df for MSE), and
+    the whole layer's backward (26df + 6d^2, 24df + 6d^2 with kept states)."""
+    for name, cfg in ti.WORKLOADS.items():
+        assert cfg.flops() > 0, name
+        if isinstance(cfg, ti.LactConfig):
+            continue
+        d, f, K, T = cfg.d_model, cfg.d_ff, cfg.conv_k, cfg.tokens
+        if cfg.layer_backward:
+            want = (24 if cfg.kept_states else 26) * d * f + 6 * d * d
+        elif cfg.backward and cfg.mode == "mse":
+            want = (10 if cfg.kept_states else 14) * d * f
+        elif cfg.backward:
+            want = (8 if cfg.kept_states else 10) * d * f
+        else:
+            want = 8 * d * f + 2 * d * d + 2 * K * d
+        assert cfg.flops() == float(T) * want, name
+
+
+def test_backward_inputs_shapes_and_seed():
+    cfg = ti.workload("inplace_bwd_bf16_128k").with_(seq_len=64, d_model=16, d_ff=24, chunk=16)
+    x = ti.backward_inputs(cfg)
+    assert [tuple(x[k].shape) for k in ("Z", "Vhat", "W_down0", "dO")] == [(1, 64, 24), (1, 64, 16), (16, 24), (1, 64, 16)]
+    assert all(t.dtype == torch.bfloat16 for t in x.values())
+    y = ti.backward_inputs(cfg)
+    assert all(torch.equal(x[k], y[k]) for k in x)
