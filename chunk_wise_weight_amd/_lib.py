@@ -12,7 +12,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libttt.so")
 
-TTT_OK, TTT_ERR_ARG, TTT_ERR_SHAPE, TTT_ERR_DTYPE, TTT_ERR_WORKSPACE, TTT_ERR_DEVICE, TTT_ERR_UNSUPPORTED = range(7)
+(TTT_OK, TTT_ERR_ARG, TTT_ERR_SHAPE, TTT_ERR_DTYPE, TTT_ERR_WORKSPACE, TTT_ERR_DEVICE, TTT_ERR_UNSUPPORTED,
+ TTT_ERR_SCRATCH_LIMIT) = range(8)
+TTT_NOALLOC_SCRATCH_BYTES = 64 << 20     # the static scratch of ttt_chunk_apply_update_noalloc
 TTT_F32, TTT_BF16 = 0, 1
 TTT_MODE_DOT, TTT_MODE_MSE, TTT_MODE_DOT_SCAN = 0, 1, 2
 TTT_UPDATE_THEN_APPLY, TTT_APPLY_THEN_UPDATE = 0, 1
@@ -57,6 +59,7 @@ _SIGNATURES = {
                                     _P, _S, _P]),
     "ttt_chunk_apply_update_ex": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.POINTER(LayerOptions), _P, _P, _P, _S, _P]),
+    "ttt_chunk_apply_update_noalloc": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F] + [_P] * 10),
     "ttt_core_apply_update": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P, _P, _P, _S, _P]),
     "ttt_core_apply_update_ex": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P,
                                       ctypes.POINTER(LayerOptions), _P, _P, _P, _S, _P]),
@@ -230,6 +233,29 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
                                            _ptr(conv_w), ctypes.byref(opts), _ptr(O), _ptr(W_final), _ptr(ws),
                                            nbytes, _stream(dev)),
            "ttt_chunk_apply_update_ex")
+    return O, W_final
+
+
+def ttt_chunk_apply_update_noalloc(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk: int, eta: float, mode,
+                                   O, W_final):
+    """The whole In-Place layer into the caller's O [B, n, d] and W_final [B, d, f] (fp32), with its scratch taken
+    from the library's static device buffer (TTT_NOALLOC_SCRATCH_BYTES): nothing is allocated here or in the
+    library.  Raises TTTError with TTT_ERR_SCRATCH_LIMIT for shapes whose scratch does not fit.  Returns (O,
+    W_final)."""
+    B, n, d = H.shape
+    f = W_gate.shape[0]
+    K = conv_w.shape[1]
+    dt, dev = H.dtype, H.device
+    for name, t, shp in (("H", H, (B, n, d)), ("X0", X0, (B, n, d)), ("W_gate", W_gate, (f, d)),
+                         ("W_up", W_up, (f, d)), ("W_down0", W_down0, (d, f)), ("W_target", W_target, (d, d)),
+                         ("conv_w", conv_w, (d, K)), ("O", O, (B, n, d))):
+        _need(t, name, shp, dt, dev)
+    _need(W_final, "W_final", (B, d, f), torch.float32, dev)
+    shape = _inplace_shape(B, n, d, f, chunk, K)
+    _check(lib().ttt_chunk_apply_update_noalloc(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
+                                                _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
+                                                _ptr(conv_w), _ptr(O), _ptr(W_final), _stream(dev)),
+           "ttt_chunk_apply_update_noalloc")
     return O, W_final
 
 

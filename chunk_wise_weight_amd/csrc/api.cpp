@@ -5,6 +5,9 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
+
+#include <hip/hip_runtime.h>
 
 #include "launch.hpp"
 #include "ttt.h"
@@ -631,6 +634,67 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
   return st;
 }
 
+// Plan and argument checks of the whole layer's call (every pointer the shape
+// needs present and 16-byte aligned, eta finite).
+int layer_plan(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* H, const void* X0,
+               const void* W_gate, const void* W_up, const void* W_down0, const void* W_target, const void* conv_w,
+               const void* O, const float* W_final, Plan* p) {
+  int st = make_plan(shape, dtype, mode, true, p);
+  if (st != TTT_OK) return st;
+  if (!finite(eta)) return TTT_ERR_ARG;
+  if (p->B > 0) {
+    if (!ok_ptr(W_down0) || !ok_ptr(W_final)) return TTT_ERR_ARG;
+    if (p->n > 0 && (!ok_ptr(H) || !ok_ptr(X0) || !ok_ptr(W_gate) || !ok_ptr(W_up) || !ok_ptr(W_target) ||
+                     !ok_ptr(conv_w) || !ok_ptr(O)))
+      return TTT_ERR_ARG;
+  }
+  return TTT_OK;
+}
+
+// ------------------------------------------------------------------ static scratch (no allocation)
+
+// The scratch of ttt_chunk_apply_update_noalloc: a device array in the
+// library's code object, so each device that loads the library holds its own
+// copy from the first use until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device copy: kernels and copies take
+// the address hipGetSymbolAddress gives for the device, kept per device below.
+static __device__ __align__(256) char scratch[TTT_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch_addr[kMaxDevices];
+
+// Makes dev the current device for the guard's lifetime.
+struct DeviceGuard {
+  int prev = -1;
+  hipError_t enter(int dev) {
+    hipError_t e = hipGetDevice(&prev);
+    if (e == hipSuccess && prev != dev) e = hipSetDevice(dev);
+    else prev = -1;
+    return e;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+// The device address of `scratch` on the device of stream s, looked up on the
+// first call for that device (with the device current) and kept.
+int static_scratch(hipStream_t s, char** out) {
+  int devid = -1;
+  if (hipStreamGetDevice(s, &devid) != hipSuccess || devid < 0 || devid >= kMaxDevices) return TTT_ERR_DEVICE;
+  char* p = g_scratch_addr[devid].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    DeviceGuard guard;
+    if (guard.enter(devid) != hipSuccess) return TTT_ERR_DEVICE;
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return TTT_ERR_DEVICE;
+    p = (char*)addr;
+    g_scratch_addr[devid].store(p, std::memory_order_release);   // every thread finds the same address
+  }
+  *out = p;
+  return TTT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -644,6 +708,9 @@ const char* ttt_status_string(int status) {
     case TTT_ERR_WORKSPACE: return "TTT_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case TTT_ERR_DEVICE: return "TTT_ERR_DEVICE: the HIP runtime rejected a launch";
     case TTT_ERR_UNSUPPORTED: return "TTT_ERR_UNSUPPORTED: sizes outside what this build handles";
+    case TTT_ERR_SCRATCH_LIMIT:
+      return "TTT_ERR_SCRATCH_LIMIT: the call needs more scratch than the static buffer of the allocation-free "
+             "entry point holds (TTT_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -663,15 +730,8 @@ int ttt_chunk_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, 
                            const void* W_target, const void* conv_w, void* O, float* W_final, void* workspace,
                            size_t workspace_bytes, void* stream) {
   Plan p;
-  int st = make_plan(shape, dtype, mode, true, &p);
+  int st = layer_plan(shape, dtype, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, &p);
   if (st != TTT_OK) return st;
-  if (!finite(eta)) return TTT_ERR_ARG;
-  if (p.B > 0) {
-    if (!ok_ptr(W_down0) || !ok_ptr(W_final)) return TTT_ERR_ARG;
-    if (p.n > 0 && (!ok_ptr(H) || !ok_ptr(X0) || !ok_ptr(W_gate) || !ok_ptr(W_up) || !ok_ptr(W_target) ||
-                    !ok_ptr(conv_w) || !ok_ptr(O)))
-      return TTT_ERR_ARG;
-  }
   if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -685,19 +745,27 @@ int ttt_chunk_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mod
                               const void* W_target, const void* conv_w, const ttt_layer_options* options, void* O,
                               float* W_final, void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
-  int st = make_plan(shape, dtype, mode, true, &p);
+  int st = layer_plan(shape, dtype, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, &p);
   if (st != TTT_OK) return st;
-  if (!finite(eta)) return TTT_ERR_ARG;
-  if (p.B > 0) {
-    if (!ok_ptr(W_down0) || !ok_ptr(W_final)) return TTT_ERR_ARG;
-    if (p.n > 0 && (!ok_ptr(H) || !ok_ptr(X0) || !ok_ptr(W_gate) || !ok_ptr(W_up) || !ok_ptr(W_target) ||
-                    !ok_ptr(conv_w) || !ok_ptr(O)))
-      return TTT_ERR_ARG;
-  }
   if ((st = check_ws(p, workspace, workspace_bytes)) != TTT_OK) return st;
   if ((st = apply_options(p, mode, options, true)) != TTT_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
+  if (dtype == TTT_BF16)
+    return layer<bf16>(p, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, ws, s);
+  return layer<float>(p, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, ws, s);
+}
+
+int ttt_chunk_apply_update_noalloc(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* H,
+                                   const void* X0, const void* W_gate, const void* W_up, const void* W_down0,
+                                   const void* W_target, const void* conv_w, void* O, float* W_final, void* stream) {
+  Plan p;
+  int st = layer_plan(shape, dtype, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, &p);
+  if (st != TTT_OK) return st;
+  if (p.total > (size_t)TTT_NOALLOC_SCRATCH_BYTES) return TTT_ERR_SCRATCH_LIMIT;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = nullptr;
+  if (p.total > 0 && (st = static_scratch(s, &ws)) != TTT_OK) return st;
   if (dtype == TTT_BF16)
     return layer<bf16>(p, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, ws, s);
   return layer<float>(p, mode, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, O, W_final, ws, s);

@@ -47,7 +47,8 @@
  *     1..8, seq_len <= 2^22 (else TTT_ERR_UNSUPPORTED); seq_len a multiple
  *     of chunk (else TTT_ERR_SHAPE).  seq_len == 0 or batch == 0 is valid: no output rows,
  *     W_final rows (if any) equal W_down0.
- *   - The library keeps no global state; calls with distinct outputs and
+ *   - The library keeps no global state (except the static scratch of
+ *     ttt_chunk_apply_update_noalloc, below); calls with distinct outputs and
  *     workspaces may run concurrently on different streams.
  */
 #ifndef TTT_H
@@ -67,7 +68,9 @@ enum {
   TTT_ERR_DTYPE = 3,        /* dtype not TTT_F32 / TTT_BF16 */
   TTT_ERR_WORKSPACE = 4,    /* workspace smaller than the query returned, or NULL when needed */
   TTT_ERR_DEVICE = 5,       /* the HIP runtime rejected a launch */
-  TTT_ERR_UNSUPPORTED = 6   /* valid but outside the sizes this build handles */
+  TTT_ERR_UNSUPPORTED = 6,  /* valid but outside the sizes this build handles */
+  TTT_ERR_SCRATCH_LIMIT = 7 /* ttt_chunk_apply_update_noalloc: the call needs more scratch than
+                               TTT_NOALLOC_SCRATCH_BYTES */
 };
 
 enum { TTT_F32 = 0, TTT_BF16 = 1 };
@@ -124,6 +127,35 @@ int ttt_chunk_apply_update(const ttt_inplace_shape* shape, int dtype, int mode, 
                            const void* W_down0, const void* W_target, const void* conv_w,
                            void* O, float* W_final, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/* Size of the static device scratch of ttt_chunk_apply_update_noalloc. */
+#define TTT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* ttt_chunk_apply_update for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same layer, arguments, outputs and errors, with no workspace
+ * argument.  The scratch the layer needs (the ttt_inplace_workspace_bytes(...,
+ * with_producers = 1, ...) of this shape, dtype and mode) comes from a static
+ * device array of TTT_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one
+ * per device: the device of `stream` holds its copy from its first call until
+ * the process ends, and that first call looks up the array's device address
+ * (with the stream's device made current for the lookup).  The call itself
+ * allocates nothing.
+ *   - A shape whose scratch exceeds TTT_NOALLOC_SCRATCH_BYTES returns
+ *     TTT_ERR_SCRATCH_LIMIT before any device work (e.g. the fp32 layer of 2048
+ *     tokens, d_model 256, d_ff 512, chunk 256 needs 16.75 MiB; the bf16 layer
+ *     of 4096 x 2 tokens, d_model 512, d_ff 1024, chunk 512, 72.5 MiB, does not
+ *     fit).
+ *   - Every call on a device shares that device's array and leaves its last
+ *     contents there; nothing in it needs to start at zero.  Calls that may
+ *     overlap on one device (several streams, several host threads) race on
+ *     it: the caller orders them, e.g. on one stream.
+ *   - The first call on a device must not be under graph capture if the
+ *     lookup would be refused there; later calls enqueue kernels only. */
+int ttt_chunk_apply_update_noalloc(const ttt_inplace_shape* shape, int dtype, int mode, float eta,
+                                   const void* H, const void* X0, const void* W_gate, const void* W_up,
+                                   const void* W_down0, const void* W_target, const void* conv_w,
+                                   void* O, float* W_final, void* stream);
 
 /* Options of ttt_chunk_apply_update_ex; a NULL options pointer, or all fields
  * zero, gives ttt_chunk_apply_update's results. */

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(7):
+    for st in range(8):
         assert cw.status_string(st).startswith("TTT_")
     assert cw.status_string(99) == "unknown status"
 
@@ -168,6 +168,27 @@ def test_call_rejects_null_and_misaligned_pointers_before_device_work():
     # bad dtype on the core entry point
     assert lib.ttt_core_apply_update(ctypes.byref(s), 5, 0, 0.1, *[_fake() for _ in range(6)], nb, None) == \
         cw.TTT_ERR_DTYPE
+
+
+def test_noalloc_entry_point_rejects_what_its_static_scratch_cannot_hold():
+    lib = cw.lib()
+    assert cw.TTT_NOALLOC_SCRATCH_BYTES == 64 << 20
+    args = [_fake() for _ in range(9)]
+    # the fp32 layer of 2048 tokens (d 256, d_ff 512, chunk 256) needs 16.75 MiB: it fits, so it passes validation
+    # (not called here: it would run); 2 x 4096 bf16 tokens at d 512, d_ff 1024, chunk 512 need 72.5 MiB
+    st, nb = _ws(_shape(), cw.TTT_F32, cw.TTT_MODE_DOT, 1)
+    assert st == cw.TTT_OK and nb <= cw.TTT_NOALLOC_SCRATCH_BYTES
+    big = _shape(B=2, n=4096, d=512, f=1024, C=512)
+    st, nb = _ws(big, cw.TTT_BF16, cw.TTT_MODE_DOT, 1)
+    assert st == cw.TTT_OK and nb > cw.TTT_NOALLOC_SCRATCH_BYTES
+    assert lib.ttt_chunk_apply_update_noalloc(ctypes.byref(big), cw.TTT_BF16, cw.TTT_MODE_DOT, 0.01, *args,
+                                              None) == cw.TTT_ERR_SCRATCH_LIMIT
+    assert "TTT_NOALLOC_SCRATCH_BYTES" in cw.status_string(cw.TTT_ERR_SCRATCH_LIMIT)
+    # argument errors come first, as for the call with a workspace
+    assert lib.ttt_chunk_apply_update_noalloc(ctypes.byref(big), cw.TTT_BF16, cw.TTT_MODE_DOT, 0.01, None,
+                                              *args[1:], None) == cw.TTT_ERR_ARG
+    assert lib.ttt_chunk_apply_update_noalloc(ctypes.byref(_shape(n=2000)), cw.TTT_BF16, 0, 0.01, *args,
+                                              None) == cw.TTT_ERR_SHAPE
 
 
 def test_step_entry_points_validate():
