@@ -237,6 +237,45 @@ def test_muon_acts_on_singular_values(shape):
     assert sv.min() > 0.6 and sv.max() < 1.25, sv
 
 
+# The quintic Newton-Schulz iteration published with the Muon optimizer (K. Jordan et al., "Muon: An optimizer for
+# hidden layers in neural networks", 2024), which the LaCT review's section 2 names without its polynomial: the
+# coefficients and the step count typed here from that publication, independently of the oracle's constants.
+PUBLISHED_ABC = (3.4445, -4.7750, 2.0315)
+PUBLISHED_STEPS = 5
+
+
+def test_muon_coefficients_are_the_published_ones():
+    assert tuple(orc.MUON_COEFFS) == PUBLISHED_ABC
+    assert orc.MUON_STEPS == PUBLISHED_STEPS
+
+
+def test_muon_rank_one_and_small_singular_values_follow_the_published_quintic():
+    """A rank-one gradient has one singular value, 1 after the Frobenius scaling: the first step maps it to
+    p(1) = a + b + c = 0.701 and five steps to 0.6964 (the published polynomial iterated by hand below).  A
+    singular value far below the largest one grows by p'(0) = a per step, a^5 = 484.9 over five steps: the
+    publication's steep slope at zero."""
+    a, b, c = PUBLISHED_ABC
+    x = 1.0
+    traj = []
+    for _ in range(PUBLISHED_STEPS):
+        x = a * x + b * x ** 3 + c * x ** 5
+        traj.append(x)
+    np.testing.assert_allclose(traj[0], 0.701, rtol=1e-12)
+    np.testing.assert_allclose(traj, [0.701, 1.113620, 0.720706, 1.089974, 0.696436], atol=1e-6)
+    rng = np.random.default_rng(42)
+    u = rng.standard_normal(6)
+    v = rng.standard_normal(4)
+    got = orc.muon(7.0 * np.outer(u, v))
+    np.testing.assert_allclose(got, traj[-1] * np.outer(u / np.linalg.norm(u), v / np.linalg.norm(v)), rtol=1e-6,
+                               atol=1e-9)
+    # diag(1, eps): the small value is multiplied by a at every step (its cubic and quintic terms vanish)
+    eps = 1e-7
+    got = orc.muon(np.diag([1.0, eps]))
+    np.testing.assert_allclose(got[0, 0], traj[-1], rtol=1e-6)
+    np.testing.assert_allclose(got[1, 1], a ** 5 * eps, rtol=1e-5)
+    np.testing.assert_allclose(a ** 5, 484.876, rtol=1e-5)
+
+
 def test_muon_update_in_the_layer():
     """One chunk: W_final = W - eta Muon(g) with g from torch autograd; the queries see it."""
     q, k, v, W1, W3, W2 = _problem(41, H=1, n=10)
