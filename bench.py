@@ -248,8 +248,9 @@ def cpu_baseline(cfg, target_s):
     from oracle import inplace as orc
     from oracle import lact as olact
 
-    info = threadpoolctl.threadpool_info()
-    cores = max([i.get("num_threads", 1) for i in info] + [1])
+    # the host cores this process may run on, with the BLAS pool sized to match
+    cores = len(os.sched_getaffinity(0))
+    threadpoolctl.threadpool_limits(limits=cores)
     if isinstance(cfg, ti.LactConfig):
         x = ti.lact_inputs(cfg)
         umask = cfg.update_mask()
