@@ -201,9 +201,10 @@ def bench_generic(cfg, steps, warmup):
     elif isinstance(cfg, ti.LactConfig):
         x = ti.lact_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
+        side = cw.LactSideStream()      # the (batch, head) rows as two chains, on the current and a side stream
         call = lambda: cw.ttt_lact_swiglu(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta,
                                           cfg.order, update_mask=cfg.update_mask(), eta_tok=g.get("eta_tok"),
-                                          loss=cfg.loss, weight_norm=cfg.weight_norm, muon=cfg.muon)
+                                          loss=cfg.loss, weight_norm=cfg.weight_norm, muon=cfg.muon, side=side)
     else:
         x = ti.inplace_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}

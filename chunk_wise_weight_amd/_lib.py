@@ -35,7 +35,29 @@ class LayerOptions(ctypes.Structure):
 
 class LactOptions(ctypes.Structure):
     _fields_ = [("order", ctypes.c_int), ("update_mask", ctypes.c_void_p), ("eta_tok", ctypes.c_void_p),
-                ("loss", ctypes.c_int), ("weight_norm", ctypes.c_int), ("muon", ctypes.c_int)]
+                ("loss", ctypes.c_int), ("weight_norm", ctypes.c_int), ("muon", ctypes.c_int),
+                ("side_stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p), ("join_event", ctypes.c_void_p)]
+
+
+class LactSideStream:
+    """A side stream and the fork / join events that let ttt_lact_swiglu run its (batch, head) rows as two chains
+    (the caller owns all three; the library creates none).  Create it outside graph capture and keep it alive while
+    calls that use it may run; calls that may be enqueued concurrently need one each."""
+
+    def __init__(self, device=None):
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.device = dev
+        self.stream = torch.cuda.Stream(device=dev)
+        self.fork = torch.cuda.Event()
+        self.join = torch.cuda.Event()
+        # torch creates an event's handle at its first record
+        self.fork.record(self.stream)
+        self.join.record(self.stream)
+        self.stream.synchronize()
+
+    def handles(self):
+        return (ctypes.c_void_p(self.stream.cuda_stream), ctypes.c_void_p(self.fork.cuda_event),
+                ctypes.c_void_p(self.join.cuda_event))
 
 
 class LactShape(ctypes.Structure):
@@ -555,13 +577,15 @@ def ttt_lact_workspace_bytes(shape: LactShape, dtype: torch.dtype) -> int:
 
 
 def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_then_apply", O=None, finals=None,
-                    workspace=None, update_mask=None, eta_tok=None, loss="mse", weight_norm=False, muon=False):
+                    workspace=None, update_mask=None, eta_tok=None, loss="mse", weight_norm=False, muon=False,
+                    side=None):
     """LaCT SwiGLU layer.  Returns (O [B, H, n, dh], W1_f, W3_f [B, H, m, dh], W2_f [B, H, dh, m]).
 
     Options (ttt_lact_swiglu_ex): update_mask, a host sequence of n // chunk flags (only the flagged chunks
     take the update step, every chunk is applied); eta_tok, per-token learning rates [B, H, n] fp32 on the
     device; loss, "mse" or "dot"; weight_norm, L2-normalise the weight rows after every update; muon, step
-    along Muon(g) (Newton-Schulz orthogonalised gradients)."""
+    along Muon(g) (Newton-Schulz orthogonalised gradients); side, a LactSideStream on the tensors' device to run
+    half of the (batch, head) rows on (None: one chain on the current stream)."""
     B, Hh, n, dh = q.shape
     m = W1.shape[1]
     dt, dev = q.dtype, q.device
@@ -582,7 +606,9 @@ def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_t
     nbytes = ttt_lact_workspace_bytes(shape, dt)
     ws = _workspace(nbytes, dev, workspace)
     ordc = _ORDERS[order] if isinstance(order, str) else int(order)
-    if update_mask is None and eta_tok is None and loss == "mse" and not weight_norm and not muon:
+    if side is not None and side.device != dev:
+        raise ValueError(f"the side stream is on {side.device}, the tensors on {dev}")
+    if update_mask is None and eta_tok is None and loss == "mse" and not weight_norm and not muon and side is None:
         _check(lib().ttt_lact_swiglu(ctypes.byref(shape), _dt(dt), ordc, float(eta), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(W1), _ptr(W3), _ptr(W2), _ptr(O), _ptr(W1f), _ptr(W3f), _ptr(W2f),
                                      _ptr(ws), nbytes, _stream(dev)), "ttt_lact_swiglu")
@@ -600,7 +626,8 @@ def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_t
         raise ValueError(f"loss must be 'mse' or 'dot', got {loss!r}")
     opts = LactOptions(ordc, ctypes.cast(mask, ctypes.c_void_p) if mask is not None else None,
                        ctypes.c_void_p(eta_tok.data_ptr()) if eta_tok is not None and eta_tok.numel() else None,
-                       1 if loss == "dot" else 0, 1 if weight_norm else 0, 1 if muon else 0)
+                       1 if loss == "dot" else 0, 1 if weight_norm else 0, 1 if muon else 0,
+                       *(side.handles() if side is not None else (None, None, None)))
     _check(lib().ttt_lact_swiglu_ex(ctypes.byref(shape), _dt(dt), float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(W1),
                                     _ptr(W3), _ptr(W2), ctypes.byref(opts), _ptr(O), _ptr(W1f), _ptr(W3f),
                                     _ptr(W2f), _ptr(ws), nbytes, _stream(dev)),

@@ -395,15 +395,16 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
 // ------------------------------------------------------------------ backward of the MSE chunk loop
 
 // Workspace of ttt_core_backward_mse: token-contiguous V^ and dO (Z is read as
-// it is), the state
-// each chunk was applied with ([k, B, d, f], chunk-major so that one chunk's
-// states are one block), the forward state and the state gradient (fp32, with
-// bf16 operand copies), and one chunk's two residual buffers [B, d, C].
+// it is), the state each chunk was applied with ([B, k, d, f], the layout of
+// the forward call's kept states), the forward state and the state gradient
+// (fp32, with bf16 operand copies), and one chunk's two residual buffers
+// [B, d, C].  With packed documents the rows' gradients go straight into
+// dW_down0 at each document start, so nothing more is needed.
 struct MsePlan {
   int64_t B, n, d, f, C, k;
   size_t esz;
   const uint8_t* docs;  // document starts [B, k] (device) or null
-  size_t off_Vt, off_Gt, off_St, off_Ws, off_Wsh, off_G, off_Gsh, off_Rt, off_Tt, off_acc, total;
+  size_t off_Vt, off_Gt, off_St, off_Ws, off_Wsh, off_G, off_Gsh, off_Rt, off_Tt, total;
 };
 
 int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p, bool saved = false) {
@@ -437,7 +438,6 @@ int make_mse_plan(const ttt_inplace_shape* s, int dtype, MsePlan* p, bool saved 
   }
   take(&p->off_Rt, B * p->d * p->C * e);
   take(&p->off_Tt, B * p->d * p->C * e);
-  take(&p->off_acc, B * DF * 4);           // per-row sums of dW_down0 over documents (packed rows)
   p->total = off;
   return TTT_OK;
 }
@@ -476,8 +476,8 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
   // the state gradient G = dLoss/dW_{c+1}, zero after the last chunk, taken back chunk by chunk
   if (st == TTT_OK) st = dev(ttt::launch_zero<float>(G, (int64_t)B * df, s));
   if (st == TTT_OK && bf) st = dev(ttt::launch_zero<T>(Gsh, (int64_t)B * df, s));
-  float* acc = (float*)(ws + p.off_acc);
-  if (st == TTT_OK && p.docs != nullptr) st = dev(ttt::launch_zero<float>(acc, (int64_t)B * df, s));
+  // packed rows: every document's gradient is added into dW_down0 at its first chunk
+  if (st == TTT_OK && p.docs != nullptr) st = dev(ttt::launch_zero<float>(dW0, df, s));
   const T* Sb = Wsaved != nullptr ? (const T*)Wsaved : (const T*)St;
   const int64_t wstride = (int64_t)k * df;
   for (int c = k - 1; c >= 0 && st == TTT_OK; --c) {
@@ -496,9 +496,10 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
     if (st == TTT_OK) st = dev(ttt::launch_mse_update<T>(Zt, Tt, W0, G, Gsh, true, B, n, d, f, C, c, s));
     // packed rows: a document's first chunk hands its gradient to dW_down0, and the one before starts from zero
     if (st == TTT_OK && p.docs != nullptr)
-      st = dev(ttt::launch_doc_grad_reset<T>(G, Gsh, acc, p.docs, B, k, c, df, s));
+      st = dev(ttt::launch_doc_grad_reset<T>(G, Gsh, dW0, p.docs, B, k, c, df, s));
   }
-  if (st == TTT_OK) st = dev(ttt::launch_sum_rows(p.docs != nullptr ? acc : G, dW0, B, df, s));
+  // (with documents, chunk 0 starts every row's first one, so every gradient is in dW_down0 by now)
+  if (st == TTT_OK && p.docs == nullptr) st = dev(ttt::launch_sum_rows(G, dW0, B, df, s));
   return st;
 }
 
@@ -1107,6 +1108,8 @@ int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta, const 
       (options->muon != 0 && options->muon != 1))
     return TTT_ERR_ARG;
   if (options->eta_tok != nullptr && !ok_ptr(options->eta_tok)) return TTT_ERR_ARG;
+  if (options->side_stream != nullptr && (options->fork_event == nullptr || options->join_event == nullptr))
+    return TTT_ERR_ARG;
   int st = check_lact(shape, dtype);
   if (st != TTT_OK) return st;
   if (order != TTT_UPDATE_THEN_APPLY && order != TTT_APPLY_THEN_UPDATE) return TTT_ERR_ARG;
@@ -1121,7 +1124,9 @@ int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta, const 
                                         : ttt::lact_workspace_bytes<float>(B, H, n, dh, m, C);
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)) return TTT_ERR_WORKSPACE;
   ttt::LactArgs a{B, H, n, dh, m, C, order, eta, q, k, v, W1, W3, W2, O, W1_f, W3_f, W2_f, (char*)workspace,
-                  options->update_mask, options->eta_tok, options->loss, options->weight_norm, options->muon};
+                  options->update_mask, options->eta_tok, options->loss, options->weight_norm, options->muon,
+                  (hipStream_t)options->side_stream, (hipEvent_t)options->fork_event,
+                  (hipEvent_t)options->join_event};
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == TTT_BF16 ? ttt::launch_lact<bf16>(a, s) : ttt::launch_lact<float>(a, s);
   if (e == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;

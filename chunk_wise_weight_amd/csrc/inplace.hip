@@ -969,22 +969,28 @@ __global__ __launch_bounds__(256) void k_keep_state(const T* __restrict__ W0, co
   store4(Ws + ((int64_t)b * k + c) * df + e, v[0], v[1], v[2], v[3]);
 }
 
-// The MSE backward at a document start (packed rows): chunk c of row b starts
-// a document, so the state gradient G[b] = dLoss/dW_c is that document's
-// contribution to dW_down0 (acc[b] += G[b]) and the previous document's last
-// chunk receives none (G[b] = 0, and its operand copy Gsh[b] if any).
+// The MSE backward at a document start (packed rows): where chunk c of row b
+// starts a document, the state gradient G[b] = dLoss/dW_c is that document's
+// contribution to dW_down0 (dW0 += G[b]) and the previous document's last
+// chunk receives none (G[b] = 0, and its operand copy Gsh[b] if any).  A thread
+// takes 4 elements of every row, rows in order, so the sum is deterministic.
 template <typename T>
 __global__ __launch_bounds__(256) void k_doc_grad_reset(float* __restrict__ G, T* __restrict__ Gsh,
-                                                        float* __restrict__ acc, const uint8_t* __restrict__ docs,
-                                                        int k, int c, int64_t df) {
+                                                        float* __restrict__ dW0, const uint8_t* __restrict__ docs,
+                                                        int B, int k, int c, int64_t df) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  const int b = blockIdx.y;
-  if (e >= df || !doc_start(docs, b, k, c)) return;
-  const int64_t o = (int64_t)b * df + e;
-  const f32x4 g = load4(G + o), a = load4(acc + o);
-  store4(acc + o, a[0] + g[0], a[1] + g[1], a[2] + g[2], a[3] + g[3]);
-  store4(G + o, 0.f, 0.f, 0.f, 0.f);
-  if (Gsh != nullptr) store4(Gsh + o, 0.f, 0.f, 0.f, 0.f);
+  if (e >= df) return;
+  f32x4 a = load4(dW0 + e);
+  bool any = false;
+  for (int b = 0; b < B; ++b) {
+    if (!doc_start(docs, b, k, c)) continue;
+    const int64_t o = (int64_t)b * df + e;
+    a += load4(G + o);
+    any = true;
+    store4(G + o, 0.f, 0.f, 0.f, 0.f);
+    if (Gsh != nullptr) store4(Gsh + o, 0.f, 0.f, 0.f, 0.f);
+  }
+  if (any) store4(dW0 + e, a[0], a[1], a[2], a[3]);
 }
 
 // dst = scale * src over n elements, four per thread (n % 4 == 0).
@@ -1360,10 +1366,10 @@ hipError_t launch_keep_state(const T* W0, const T* Wcur, T* Ws, const uint8_t* d
 }
 
 template <typename T>
-hipError_t launch_doc_grad_reset(float* G, T* Gsh, float* acc, const uint8_t* docs, int B, int k, int c, int64_t df,
+hipError_t launch_doc_grad_reset(float* G, T* Gsh, float* dW0, const uint8_t* docs, int B, int k, int c, int64_t df,
                                  hipStream_t s) {
   if (B == 0 || df == 0) return hipSuccess;
-  k_doc_grad_reset<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(G, Gsh, acc, docs, k, c, df);
+  k_doc_grad_reset<T><<<(unsigned)cdiv(df / 4, 256), 256, 0, s>>>(G, Gsh, dW0, docs, B, k, c, df);
   return hipGetLastError();
 }
 

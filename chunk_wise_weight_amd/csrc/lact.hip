@@ -20,9 +20,7 @@
 // separate streams (see launch_lact).
 // Layouts: q, k, v, O [BH, n, dh]; W1, W3 [H, m, dh]; W2 [H, dh, m];
 // states W1f, W3f [BH, m, dh], W2f [BH, dh, m] (fp32).
-#include <mutex>
 #include <type_traits>
-#include <vector>
 
 #include "gemm.hpp"
 #include "launch.hpp"
@@ -652,46 +650,6 @@ size_t lact_workspace_bytes(int B, int H, int n, int dh, int m, int C) {
 
 namespace {
 
-// Per-device side streams and the fork / join events of one call, created on
-// first use and kept until the process ends.  The lock is held while a call
-// enqueues its work, so that the record / wait pairs of concurrent calls on one
-// device do not interleave.
-struct SideStreams {
-  hipStream_t st[kGroups - 1] = {};
-  hipEvent_t fork = nullptr, join[kGroups - 1] = {};
-};
-std::mutex g_side_mu;
-std::vector<SideStreams> g_side;
-
-// Called with the lock held and dev the current device.
-hipError_t side_streams(int dev, SideStreams*& out) {
-  if ((int)g_side.size() <= dev) g_side.resize(dev + 1);
-  SideStreams& ss = g_side[dev];
-  hipError_t e;
-  for (int i = 0; i < kGroups - 1; ++i) {
-    if (ss.st[i] == nullptr && (e = hipStreamCreateWithFlags(&ss.st[i], hipStreamNonBlocking)) != hipSuccess) return e;
-    if (ss.join[i] == nullptr && (e = hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming)) != hipSuccess)
-      return e;
-  }
-  if (ss.fork == nullptr && (e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
-  out = &ss;
-  return hipSuccess;
-}
-
-// Makes dev the current device for the guard's lifetime.
-struct DeviceGuard {
-  int prev = -1;
-  hipError_t enter(int dev) {
-    hipError_t e = hipGetDevice(&prev);
-    if (e == hipSuccess && prev != dev) e = hipSetDevice(dev);
-    else prev = -1;
-    return e;
-  }
-  ~DeviceGuard() {
-    if (prev >= 0) (void)hipSetDevice(prev);
-  }
-};
-
 // One group: rows [bh0, bh0 + BH) of the call, with its workspace region;
 // only its launches first .. last - 1 (in enqueue order) are enqueued.
 template <typename T>
@@ -804,50 +762,34 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
 
 }  // namespace
 
-// Group 0 runs on the caller's stream s, group g >= 1 on side stream g - 1 of
-// s's device, between a fork event recorded on s (after group 0's lead) and
-// join events that s waits for, so that the whole call is ordered on s like a
-// single launch.
+// Without a side stream the rows run as one chain on s.  With one, group 0
+// runs on s and group 1 on the side stream, between the fork event recorded
+// on s (after group 0's lead) and the join event that s waits for, so that the
+// whole call is ordered on s like a single launch.  The side stream and both
+// events belong to the caller.
 template <typename T>
 hipError_t launch_lact(const LactArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   if (BH == 0) return hipSuccess;
-  const int G = BH < kGroups ? BH : kGroups;
-  size_t off[kGroups] = {};
-  for (int g = 1; g < G; ++g)
-    off[g] = off[g - 1] + lact_layout<T>(group_rows(BH, G, g - 1), a.dh, a.m, a.C).total;
+  const int G = a.side == nullptr ? 1 : (BH < kGroups ? BH : kGroups);
   if (G == 1) return enqueue_lact_group<T>(a, 0, BH, a.ws, s);
-
-  int dev;
-  hipError_t e = hipStreamGetDevice(s, &dev);
+  static_assert(kGroups == 2, "one side stream");
+  const int rows0 = group_rows(BH, G, 0);
+  const size_t off1 = lact_layout<T>(rows0, a.dh, a.m, a.C).total;
+  hipError_t e = enqueue_lact_group<T>(a, 0, rows0, a.ws, s, 0, kLead);
   if (e != hipSuccess) return e;
-  DeviceGuard guard;
-  if ((e = guard.enter(dev)) != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  SideStreams* ss;
-  if ((e = side_streams(dev, ss)) != hipSuccess) return e;
-  e = enqueue_lact_group<T>(a, 0, group_rows(BH, G, 0), a.ws, s, 0, kLead);
-  if (e != hipSuccess) return e;
-  if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
-  hipError_t first = hipSuccess;
-  int bh0 = group_rows(BH, G, 0);
-  for (int g = 1; g < G; ++g) {
-    const int rows = group_rows(BH, G, g);
-    e = hipStreamWaitEvent(ss->st[g - 1], ss->fork, 0);
-    if (e == hipSuccess) e = enqueue_lact_group<T>(a, bh0, rows, a.ws + off[g], ss->st[g - 1]);
-    if (first == hipSuccess) first = e;
-    // the join is recorded even after an error, so that s never runs ahead of
-    // work already enqueued on the side stream
-    e = hipEventRecord(ss->join[g - 1], ss->st[g - 1]);
-    if (first == hipSuccess) first = e;
-    bh0 += rows;
-  }
-  e = enqueue_lact_group<T>(a, 0, group_rows(BH, G, 0), a.ws, s, kLead);
+  if ((e = hipEventRecord(a.fork, s)) != hipSuccess) return e;
+  e = hipStreamWaitEvent(a.side, a.fork, 0);
+  if (e == hipSuccess) e = enqueue_lact_group<T>(a, rows0, group_rows(BH, G, 1), a.ws + off1, a.side);
+  hipError_t first = e;
+  // the join is recorded even after an error, so that s never runs ahead of
+  // work already enqueued on the side stream
+  e = hipEventRecord(a.join, a.side);
   if (first == hipSuccess) first = e;
-  for (int g = 1; g < G; ++g) {
-    e = hipStreamWaitEvent(s, ss->join[g - 1], 0);
-    if (first == hipSuccess) first = e;
-  }
+  e = enqueue_lact_group<T>(a, 0, rows0, a.ws, s, kLead);
+  if (first == hipSuccess) first = e;
+  e = hipStreamWaitEvent(s, a.join, 0);
+  if (first == hipSuccess) first = e;
   return first;
 }
 

@@ -92,9 +92,10 @@ template <typename T>
 hipError_t launch_mse_apply_gen(const T* Zt, const T* Vt, const T* W0, const T* Wcur, T* O, T* Rt, bool cont, int B,
                                 int n, int d, int f, int C, int c, float rscale, float vscale, float oscale, bool gen,
                                 hipStream_t s, int64_t wstride = 0);
-// MSE backward, packed rows: where chunk c starts row b's document, acc[b] += G[b] and G[b] (and Gsh[b]) = 0.
+// MSE backward, packed rows: where chunk c starts row b's document, dW0 += G[b] (rows in order) and G[b] (and
+// Gsh[b]) = 0.
 template <typename T>
-hipError_t launch_doc_grad_reset(float* G, T* Gsh, float* acc, const uint8_t* docs, int B, int k, int c, int64_t df,
+hipError_t launch_doc_grad_reset(float* G, T* Gsh, float* dW0, const uint8_t* docs, int B, int k, int c, int64_t df,
                                  hipStream_t s);
 // Ws [B, k, d, f]: slot c gets the state the MSE apply of chunk c reads (W_down0
 // where a document starts, else Wcur [B, d, f]).
@@ -144,6 +145,8 @@ struct LactArgs {
   int loss_dot;                       // 1: dot-product loss -f(k)^T v; 0: squared error
   int weight_norm;                    // 1: L2-normalise the rows of W1, W3, W2 after every update
   int muon;                           // 1: step along Muon(g) (Newton-Schulz) instead of g
+  hipStream_t side;                   // caller's side stream for the second row group, or null: one chain
+  hipEvent_t fork, join;              // caller's events ordering the side stream's work within the call
 };
 template <typename T>
 size_t lact_workspace_bytes(int B, int H, int n, int dh, int m, int C);

@@ -22,18 +22,17 @@
  * Conventions common to every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller (e.g.
  *     torch.Tensor.data_ptr()), row-major and contiguous, 16-byte aligned.
- *     The library allocates no device memory; scratch comes from the
- *     caller's workspace, whose size the matching *_workspace_bytes call
- *     returns.  (ttt_lact_swiglu creates one side stream and its events per
- *     device on first use and keeps them.)
+ *     The library allocates no device memory and creates no streams or
+ *     events; scratch comes from the caller's workspace, whose size the
+ *     matching *_workspace_bytes call returns.
  *   - Inputs are read only.  Outputs and workspace must not alias inputs or
  *     each other.  W_down0 is never written: "in place" names the reuse of
  *     the MLP's own weight as the fast weight, not memory aliasing.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
  *     the default stream).  The call returns once the work is enqueued.  It
- *     enqueues kernels only (no copy or memset; ttt_lact_swiglu adds an event
- *     fork and join), so a call can be captured into a HIP graph and replayed
- *     with the same buffers.
+ *     enqueues kernels only (no copy or memset; ttt_lact_swiglu_ex given a
+ *     side stream adds an event fork and join), so a call can be captured
+ *     into a HIP graph and replayed with the same buffers.
  *   - Every argument is validated before any device work is enqueued; on an
  *     error status nothing has been enqueued and outputs are untouched.  A
  *     launch failure reported by the runtime returns TTT_ERR_DEVICE, in which
@@ -278,7 +277,7 @@ int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, cons
 
 /* Workspace bytes for ttt_core_backward_mse, with the states given
  * (saved_states = 1) or recomputed (0): about B (k d f + 2 n d) dtype
- * elements plus 3 B d f fp32, without the k d f and one B d f fp32 when the
+ * elements plus 2 B d f fp32, without the k d f and one B d f fp32 when the
  * states are given. */
 int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states,
                                           size_t* bytes);
@@ -436,12 +435,8 @@ int ttt_lact_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* byt
  *   W1_f, W3_f [B, H, m, dh]  fp32    final states (written)
  *   W2_f      [B, H, dh, m]   fp32
  * Supported: head_dim, hidden, chunk multiples of 8; seq_len % chunk == 0.
- * Streams: with two or more (batch, head) rows, half of the rows run on a side
- * stream of the stream's device that the library creates on first use and
- * keeps; the side work starts after everything enqueued on `stream` before
- * the call and everything enqueued on `stream` after the call waits for it
- * (event fork and join), so the call is ordered on `stream` like one kernel.
- * Calls from several host threads on one device enqueue one at a time. */
+ * Every launch is enqueued on `stream` (ttt_lact_swiglu_ex can split the rows
+ * over a second stream the caller provides). */
 int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta,
                     const void* q, const void* k, const void* v,
                     const void* W1, const void* W3, const void* W2,
@@ -482,6 +477,21 @@ typedef struct {
    * layer's dtype with fp32 accumulation.  0: plain gradient.  Other values:
    * TTT_ERR_ARG. */
   int muon;
+  /* Two chains: side_stream (a hipStream_t of the same device as `stream`)
+   * runs the second half of the (batch, head) rows while `stream` runs the
+   * first half, so that one chain's epilogues and short launches overlap the
+   * other's contractions.  fork_event and join_event (hipEvent_t, e.g. created
+   * with hipEventDisableTiming) order it: the side work starts after
+   * everything enqueued on `stream` before the call, and everything enqueued
+   * on `stream` after the call waits for it, so the call is ordered on
+   * `stream` like one kernel.  All three belong to the caller (created,
+   * destroyed, and not shared by calls that may be enqueued concurrently).
+   * NULL side_stream: every row runs in one chain on `stream` (the events are
+   * not read).  A side stream without both events: TTT_ERR_ARG.  With a
+   * single row the side stream is not used. */
+  void* side_stream;
+  void* fork_event;
+  void* join_event;
 } ttt_lact_options;
 
 /* The LaCT layer of ttt_lact_swiglu with options (above; NULL options:

@@ -308,8 +308,8 @@ def test_mse_backward_validation():
 
     # V^ and dO token-contiguous, the state gradient (fp32 + bf16 copy), two chunk residual buffers; the recomputing
     # call adds the chunk-major states, the forward state and its bf16 copy
-    common = 2 * al(B * n * d * e) + al(B * d * f * 4) + al(B * d * f * e) + 2 * al(B * d * C * e) + \
-        al(B * d * f * 4)     # + the per-row dW_down0 sums of packed rows
+    # (packed rows add each document's gradient into dW_down0 directly: no per-row sums)
+    common = 2 * al(B * n * d * e) + al(B * d * f * 4) + al(B * d * f * e) + 2 * al(B * d * C * e)
     assert ws(1) == common
     assert ws(0) == common + al(k * B * d * f * e) + al(B * d * f * 4) + al(B * d * f * e)
     ins = [_fake() for _ in range(4)]      # Z, Vhat, W_down0, dO
@@ -350,6 +350,11 @@ def test_lact_validation():
     args = [_fake() for _ in range(10)]
     assert lib.ttt_lact_swiglu(ctypes.byref(good), cw.TTT_BF16, 7, 1.0, *args, _fake(), out.value, None) == \
         cw.TTT_ERR_ARG
+    # a side stream needs both of its events
+    for fork, join in ((None, _fake()), (_fake(), None), (None, None)):
+        opts = cw.LactOptions(0, None, None, 0, 0, 0, _fake(), fork, join)
+        assert lib.ttt_lact_swiglu_ex(ctypes.byref(good), cw.TTT_BF16, 1.0, *args[:6], ctypes.byref(opts),
+                                      *args[6:], _fake(), out.value, None) == cw.TTT_ERR_ARG
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,7 +1,7 @@
 """The layer calls captured into HIP graphs (torch.cuda.CUDAGraph drives the capture).
 
-The library enqueues kernels only -- no allocation, copy or memset -- and the LaCT call adds an event fork and
-join with a side stream, which a capture records as parallel branches.  The backward entry points (the dot and MSE
+The library enqueues kernels only -- no allocation, copy or memset -- and the LaCT call given a side stream adds
+an event fork and join with it, which a capture records as parallel branches.  The backward entry points (the dot and MSE
 chunk loops, the whole dot layer) are captured the same way.  Each graph is replayed three times with
 the outputs clobbered, eager calls and synchronisations in between, and every replay must reproduce the eager
 call's bits.
@@ -24,11 +24,12 @@ def _inplace(mode):
     return lambda: cw.ttt_chunk_apply_update(*args)
 
 
-def _lact():
+def _lact(two_chains):
     cfg = ti.LactConfig("graph", 1, 3, 512, 64, 128, 128, 0.7, "update_then_apply", "bf16", seed=17)
     g = {k: v.cuda() for k, v in ti.lact_inputs(cfg).items()}
     args = (g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta, cfg.order)
-    return lambda: cw.ttt_lact_swiglu(*args)
+    side = cw.LactSideStream() if two_chains else None     # created before the capture
+    return lambda: cw.ttt_lact_swiglu(*args, side=side)
 
 
 def _backward(kind):
@@ -43,9 +44,10 @@ def _backward(kind):
     return lambda: fn(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta)
 
 
-@pytest.mark.parametrize("kind", ["dot", "mse", "lact", "backward", "mse_backward", "layer_backward"])
+@pytest.mark.parametrize("kind", ["dot", "mse", "lact", "lact_side", "backward", "mse_backward", "layer_backward"])
 def test_graph_replays_match_eager(kind):
-    call = _lact() if kind == "lact" else _backward(kind) if "backward" in kind else _inplace(kind)
+    call = (_lact(kind == "lact_side") if kind.startswith("lact") else _backward(kind) if "backward" in kind
+            else _inplace(kind))
     eager = call()
     torch.cuda.synchronize()
     # warm-up on a side stream, as torch asks before a capture

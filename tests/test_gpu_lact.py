@@ -80,15 +80,18 @@ def test_lact_eta_zero_is_plain_swiglu():
     assert np.array_equal(f64(W2f[0]), ti.to_f64(x["W2"]))
 
 
+@pytest.mark.parametrize("two_chains", [False, True])
 @pytest.mark.parametrize("B,H", [(1, 3), (3, 1), (2, 2)])
-def test_lact_rows_equal_single_row_calls(B, H):
-    """Every (batch, head) row is an independent fast weight.  A call on B x H rows (split into groups whose
-    chains run on separate streams, unevenly for 3 rows) gives each row bit for bit what a call on that row alone
-    gives, and a repeated call gives the same bits."""
+def test_lact_rows_equal_single_row_calls(B, H, two_chains):
+    """Every (batch, head) row is an independent fast weight.  A call on B x H rows (in one chain, or split into
+    two groups whose chains run on the caller's stream and a side stream, unevenly for 3 rows) gives each row bit
+    for bit what a call on that row alone gives, and a repeated call gives the same bits."""
     cfg = cfg_small("bf16", B=B, H=H, n=384, dh=64, m=128, C=128, eta=0.7, seed=11)
     x = ti.lact_inputs(cfg)
     g = {k: v.cuda() for k, v in x.items()}
-    call = lambda q, k, v, W1, W3, W2: cw.ttt_lact_swiglu(q, k, v, W1, W3, W2, cfg.chunk, cfg.eta, cfg.order)
+    side = cw.LactSideStream() if two_chains else None
+    call = lambda q, k, v, W1, W3, W2: cw.ttt_lact_swiglu(q, k, v, W1, W3, W2, cfg.chunk, cfg.eta, cfg.order,
+                                                          side=side)
     full = call(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"])
     again = call(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"])
     torch.cuda.synchronize()
@@ -107,15 +110,18 @@ def test_lact_rows_equal_single_row_calls(B, H):
 @pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
 def test_lact_update_mask(dtype, order):
     """Strided update (ttt_lact_swiglu_ex, option update_mask): only the flagged chunks take the gradient step, every chunk is
-    applied, against the oracle with the same mask on 2 x 2 rows (both stream groups); the first chunk is masked,
-    which leaves the first update-then-apply step with nothing to do.  An all-on mask gives the unmasked call's
-    bits."""
+    applied, against the oracle with the same mask on 2 x 2 rows (run as two chains with a side stream); the first
+    chunk is masked, which leaves the first update-then-apply step with nothing to do.  An all-on mask gives the
+    unmasked call's bits, and one chain the two chains' bits."""
     cfg = cfg_small(dtype, order, B=2, H=2, n=768, dh=64, m=128, C=128, eta=0.8, seed=21)
     mask = [0, 1, 1, 0, 1, 0]
     x = ti.lact_inputs(cfg)
     g = {k: v.cuda() for k, v in x.items()}
     args = (g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta, cfg.order)
-    got = cw.ttt_lact_swiglu(*args, update_mask=mask)
+    got = cw.ttt_lact_swiglu(*args, update_mask=mask, side=cw.LactSideStream())
+    one_chain = cw.ttt_lact_swiglu(*args, update_mask=mask)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(got, one_chain))
     plain = cw.ttt_lact_swiglu(*args)
     all_on = cw.ttt_lact_swiglu(*args, update_mask=[1] * len(mask))
     torch.cuda.synchronize()
