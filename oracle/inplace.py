@@ -348,14 +348,16 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
     return O, W_final
 
 
-def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, dO, doc_starts=None):
-    """Gradients of a loss that depends on the output O of the dot-objective
-    layer (inplace_layer with mode "dot", the causal convolution, one document
-    per row), given dO = dLoss/dO [B, n, d].  Returns (dH, dX0 [B, n, d],
-    dW_gate, dW_up [f, d], dW_down0 [d, f], dW_target [d, d], dconv_w [d, K]).
+def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, dO, doc_starts=None, mode="dot"):
+    """Gradients of a loss that depends on the output O of the layer
+    (inplace_layer with the causal convolution, one document per row, and the
+    objective `mode`, "dot" or "mse"), given dO = dLoss/dO [B, n, d].  Returns
+    (dH, dX0 [B, n, d], dW_gate, dW_up [f, d], dW_down0 [d, f],
+    dW_target [d, d], dconv_w [d, K]).
 
     The chain rule through the layer's definitions, one step at a time:
-      * the chunk loop (chunk_core_backward, per row) gives dZ, dVhat and the
+      * the chunk loop (chunk_core_backward for the dot objective,
+        mse_core_backward for the MSE one, per row) gives dZ, dVhat and the
         row's part of dW_down0;
       * Z = silu(A) * U with A = H W_gate^T and U = H W_up^T (eq. (2)):
         dA = dZ * U * silu'(A) and dU = dZ * silu(A), where
@@ -381,7 +383,7 @@ def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, d
             k = len(doc_starts[b])
             cuts = [c * chunk for c in range(k) if c == 0 or doc_starts[b][c]] + [min(k * chunk, len(H[b]))]
             parts = [layer_backward(H[b:b + 1, a:e], X0[b:b + 1, a:e], W_gate, W_up, W_down0, W_target, conv_w,
-                                    chunk, eta, dO[b:b + 1, a:e]) for a, e in zip(cuts[:-1], cuts[1:])]
+                                    chunk, eta, dO[b:b + 1, a:e], mode=mode) for a, e in zip(cuts[:-1], cuts[1:])]
             outs.append((np.concatenate([q[0] for q in parts], axis=1), np.concatenate([q[1] for q in parts], axis=1),
                          *[sum(q[i] for q in parts) for i in range(2, 7)]))
         return (np.concatenate([o[0] for o in outs]), np.concatenate([o[1] for o in outs]),
@@ -400,7 +402,8 @@ def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, d
         Z = A * sg * U
         Y = causal_depthwise_conv1d(X0[b], cw)
         V = Y @ Wt
-        dZ, dV, dW0_b = chunk_core_backward(Z, V, W0, chunk, eta, dO[b])
+        core = {"dot": chunk_core_backward, "mse": mse_core_backward}[mode]
+        dZ, dV, dW0_b = core(Z, V, W0, chunk, eta, dO[b])
         dW0 += dW0_b
         dA = dZ * U * (sg * (1.0 + A * (1.0 - sg)))
         dU = dZ * (A * sg)

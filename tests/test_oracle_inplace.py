@@ -617,6 +617,76 @@ def test_layer_backward_finite_differences():
         assert abs((L(p) - L(m)) / (2 * h) - g) < 1e-6 * max(1.0, abs(g)), (which, idx)
 
 
+def _torch_mse_layer(H, X0, Wg, Wu, W0, Wt, cw, C, eta):
+    """The MSE-objective layer written with torch float64 primitives (F.silu, grouped conv1d with left padding, the
+    MSE chunk loop), for autograd."""
+    import torch.nn.functional as F
+    B, n, d = H.shape
+    K = cw.shape[1]
+    Z = F.silu(H @ Wg.T) * (H @ Wu.T)
+    Y = F.conv1d(F.pad(X0.transpose(1, 2), (K - 1, 0)), cw[:, None, :], groups=d).transpose(1, 2)
+    V = Y @ Wt
+    return torch.stack([_torch_mse_chunk_loop(Z[b], V[b], W0, C, eta) for b in range(B)])
+
+
+@pytest.mark.parametrize("n,C,K", [(12, 4, 3), (10, 5, 1), (9, 3, 4), (8, 8, 2)])
+def test_mse_layer_backward_matches_autograd(n, C, K):
+    """Every gradient of the whole MSE-objective layer (producers, causal conv, target projection, the in-order
+    MSE scan) against torch autograd of the same layer built from torch's own silu and grouped conv1d, two batch
+    rows sharing the weights; one case is a single chunk, where the targets reach no output (dX0, dW_target and
+    the conv taps' gradients are exactly zero)."""
+    rng = _rng(56)
+    B, d, f, eta = 2, 3, 5, 0.6
+    shapes = ((B, n, d), (B, n, d), (f, d), (f, d), (d, f), (d, d), (d, K))
+    H, X0, Wg, Wu, W0, Wt, cw = (rng.standard_normal(s) * 0.7 for s in shapes)
+    dO = rng.standard_normal((B, n, d))
+    ours = orc.layer_backward(H, X0, Wg, Wu, W0, Wt, cw, C, eta, dO, mode="mse")
+    ts = [torch.tensor(a, requires_grad=True) for a in (H, X0, Wg, Wu, W0, Wt, cw)]
+    (_torch_mse_layer(*ts, C, eta) * torch.from_numpy(dO)).sum().backward()
+    for got, t in zip(ours, ts):
+        want = np.zeros(t.shape) if t.grad is None else t.grad.numpy()
+        np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-11)
+    if n == C:
+        assert not ours[1].any() and not ours[5].any() and not ours[6].any()
+    O, _ = orc.inplace_layer(H, X0, Wg, Wu, W0, Wt, cw, C, eta, "mse")
+    np.testing.assert_allclose(O, _torch_mse_layer(*[t.detach() for t in ts], C, eta).numpy(), rtol=1e-12,
+                               atol=1e-12)
+
+
+def test_mse_layer_backward_finite_differences_and_documents():
+    """Central differences of <O, dO> through the oracle's MSE layer for entries of the conv taps, W_target,
+    W_gate, W_down0 and X0; and with packed documents, the row's gradients equal those of its documents taken as
+    separate rows (activation gradients side by side, weight gradients added)."""
+    rng = _rng(57)
+    B, n, C, d, f, K, eta = 1, 8, 4, 2, 3, 3, 0.5
+    shapes = ((B, n, d), (B, n, d), (f, d), (f, d), (d, f), (d, d), (d, K))
+    args = [rng.standard_normal(s) * 0.7 for s in shapes]
+    dO = rng.standard_normal((B, n, d))
+    grads = orc.layer_backward(*args, C, eta, dO, mode="mse")
+    L = lambda a: float(np.sum(orc.inplace_layer(*a, C, eta, "mse")[0] * dO))
+    h = 1e-6
+    for which, idx in ((6, (1, 0)), (6, (0, 2)), (5, (1, 0)), (2, (2, 1)), (4, (1, 2)), (1, (0, 2, 1))):
+        p = [a.copy() for a in args]
+        m = [a.copy() for a in args]
+        p[which][idx] += h
+        m[which][idx] -= h
+        g = grads[which][idx]
+        assert abs((L(p) - L(m)) / (2 * h) - g) < 1e-6 * max(1.0, abs(g)), (which, idx)
+    # documents of 2 and 1 chunks in one row of 3 chunks
+    n2 = 12
+    shapes = ((1, n2, d), (1, n2, d), (f, d), (f, d), (d, f), (d, d), (d, K))
+    args = [rng.standard_normal(s) * 0.7 for s in shapes]
+    dO = rng.standard_normal((1, n2, d))
+    packed = orc.layer_backward(*args, C, eta, dO, doc_starts=np.array([[1, 0, 1]]), mode="mse")
+    first = orc.layer_backward(args[0][:, :8], args[1][:, :8], *args[2:], C, eta, dO[:, :8], mode="mse")
+    second = orc.layer_backward(args[0][:, 8:], args[1][:, 8:], *args[2:], C, eta, dO[:, 8:], mode="mse")
+    for i in (0, 1):
+        np.testing.assert_allclose(packed[i], np.concatenate([first[i], second[i]], axis=1), rtol=1e-12,
+                                   atol=1e-12)
+    for i in range(2, 7):
+        np.testing.assert_allclose(packed[i], first[i] + second[i], rtol=1e-12, atol=1e-12)
+
+
 def _masked_dual_form_dot(Z, V, W0, C, eta, mask):
     """The dual form above with the update mask: token s of an earlier chunk contributes only if its chunk is
     flagged."""
