@@ -156,16 +156,17 @@ def bench_generic(cfg, steps, warmup):
         if cfg.kept_states:
             # the forward layer keeps its states (before the timed region, like the other inputs)
             Ws = torch.empty(B, n // cfg.chunk, d, f, dtype=dt, device="cuda")
-            cw.ttt_chunk_apply_update(*w, cfg.chunk, cfg.eta, W_states=Ws)
+            cw.ttt_chunk_apply_update(*w, cfg.chunk, cfg.eta, cfg.mode, W_states=Ws)
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
         grads = tuple(torch.empty(*shp, dtype=t, device="cuda") for shp, t in (
             ((B, n, d), dt), ((B, n, d), dt), ((f, d), torch.float32), ((f, d), torch.float32),
             ((d, f), torch.float32), ((d, d), torch.float32), ((d, K), torch.float32)))
         shape = cw.InplaceShape(B, n, d, f, cfg.chunk, K)
-        nbytes = cw.ttt_layer_backward_workspace_bytes(shape, dt, cfg.kept_states)
+        nbytes = cw.ttt_layer_backward_workspace_bytes(shape, dt, cfg.kept_states, cfg.mode)
         ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
-        call = lambda: cw.ttt_layer_backward(*w, dO, cfg.chunk, cfg.eta, W_states=Ws, grads=grads, workspace=ws)
+        call = lambda: cw.ttt_layer_backward(*w, dO, cfg.chunk, cfg.eta, W_states=Ws, grads=grads, workspace=ws,
+                                             mode=cfg.mode)
     elif getattr(cfg, "backward", False):
         x = ti.backward_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
@@ -270,7 +271,7 @@ def cpu_baseline(cfg, target_s):
         run = lambda kc: orc.layer_backward(ti.to_f64(x["H"][:1, : kc * cfg.chunk]),
                                             ti.to_f64(x["X0"][:1, : kc * cfg.chunk]), ws["W_gate"], ws["W_up"],
                                             ws["W_down0"], ws["W_target"], ws["conv_w"], cfg.chunk, cfg.eta,
-                                            ti.to_f64(dO[:1, : kc * cfg.chunk]))
+                                            ti.to_f64(dO[:1, : kc * cfg.chunk]), mode=cfg.mode)
     elif cfg.backward:
         x = ti.backward_inputs(cfg)
         W0 = ti.to_f64(x["W_down0"])

@@ -8,7 +8,7 @@ missing or no GPU is present the calls raise.
 
 Functions keep the C names:
   ttt_chunk_apply_update, ttt_chunk_apply_update_noalloc, ttt_core_apply_update(_ex), ttt_core_backward,
-  ttt_core_backward_mse, ttt_layer_backward, ttt_produce_z,
+  ttt_core_backward_mse, ttt_layer_backward, ttt_layer_backward_mse, ttt_produce_z,
   ttt_produce_vhat, ttt_chunk_delta, ttt_chunk_scan, ttt_chunk_update_scan,
   ttt_chunk_apply, ttt_lact_swiglu, plus the workspace queries.
 """
@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     lib, lib_path, exported_symbols, status_string,
     ttt_inplace_workspace_bytes, ttt_lact_workspace_bytes, ttt_vhat_workspace_bytes, ttt_update_scan_workspace_bytes,
     ttt_core_backward_workspace_bytes, ttt_core_backward, ttt_layer_backward_workspace_bytes, ttt_layer_backward,
+    ttt_layer_backward_mse_workspace_bytes, ttt_layer_backward_mse,
     ttt_core_backward_mse_workspace_bytes, ttt_core_backward_mse,
     ttt_chunk_apply_update, ttt_chunk_apply_update_noalloc, ttt_core_apply_update, ttt_produce_z, ttt_produce_vhat,
     ttt_chunk_delta, ttt_chunk_scan, ttt_chunk_update_scan, ttt_chunk_apply, ttt_lact_swiglu,

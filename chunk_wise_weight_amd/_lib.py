@@ -91,6 +91,8 @@ _SIGNATURES = {
                                    _S, _P]),
     "ttt_layer_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
     "ttt_layer_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 18 + [_S, _P]),
+    "ttt_layer_backward_mse_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
+    "ttt_layer_backward_mse": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 18 + [_S, _P]),
     "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                                _P]),
     "ttt_produce_z": (_I, [ctypes.POINTER(InplaceShape), _I, _P, _P, _P, _P, _P, _P]),
@@ -400,20 +402,34 @@ def ttt_core_backward_mse(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None,
     return dZ, dVhat, dW_down0
 
 
-def ttt_layer_backward_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, saved_states=False) -> int:
+def ttt_layer_backward_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, saved_states=False,
+                                       mode="dot") -> int:
     n = ctypes.c_size_t()
-    _check(lib().ttt_layer_backward_workspace_bytes(ctypes.byref(shape), _dt(dtype), int(bool(saved_states)),
-                                                    ctypes.byref(n)),
-           "ttt_layer_backward_workspace_bytes")
+    name = "ttt_layer_backward_mse_workspace_bytes" if mode == "mse" else "ttt_layer_backward_workspace_bytes"
+    _check(getattr(lib(), name)(ctypes.byref(shape), _dt(dtype), int(bool(saved_states)), ctypes.byref(n)), name)
     return n.value
 
 
+def ttt_layer_backward_mse_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, saved_states=False) -> int:
+    return ttt_layer_backward_workspace_bytes(shape, dtype, saved_states, "mse")
+
+
+def ttt_layer_backward_mse(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk: int, eta: float,
+                           W_states=None, grads=None, workspace=None, doc_starts=None):
+    """ttt_layer_backward for the MSE objective (see there)."""
+    return ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk, eta, W_states, grads,
+                              workspace, doc_starts, mode="mse")
+
+
 def ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk: int, eta: float, W_states=None,
-                       grads=None, workspace=None, doc_starts=None):
-    """Gradients of the dot layer with respect to every input, given dO = dLoss/dO [B, n, d], with the per-chunk
-    states W_states kept by the forward call or recomputed (None), and doc_starts [B, n // chunk] packing documents
-    as for the forward layer.  Returns (dH, dX0, dW_gate, dW_up, dW_down0,
-    dW_target, dconv_w): activations in the inputs' dtype, weight gradients fp32 summed over the batch rows."""
+                       grads=None, workspace=None, doc_starts=None, mode="dot"):
+    """Gradients of the layer (objective `mode`, "dot" or "mse") with respect to every input, given
+    dO = dLoss/dO [B, n, d], with the per-chunk states W_states kept by the forward call or recomputed (None), and
+    doc_starts [B, n // chunk] packing documents as for the forward layer.  Returns (dH, dX0, dW_gate, dW_up,
+    dW_down0, dW_target, dconv_w): activations in the inputs' dtype, weight gradients fp32 summed over the batch
+    rows."""
+    if mode not in ("dot", "mse"):
+        raise ValueError(f"mode must be 'dot' or 'mse', got {mode!r}")
     B, n, d = H.shape
     f = W_gate.shape[0]
     K = conv_w.shape[1]
@@ -431,15 +447,15 @@ def ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk
     if W_states is not None:
         _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
     shape = _inplace_shape(B, n, d, f, chunk, K)
-    nbytes = ttt_layer_backward_workspace_bytes(shape, dt, W_states is not None)
+    nbytes = ttt_layer_backward_workspace_bytes(shape, dt, W_states is not None, mode)
     ws = _workspace(nbytes, dev, workspace)
     sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
     doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
     dp = ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None and doc_starts.numel() else None
-    _check(lib().ttt_layer_backward(ctypes.byref(shape), _dt(dt), float(eta), _ptr(H), _ptr(X0), _ptr(W_gate),
-                                    _ptr(W_up), _ptr(W_down0), _ptr(W_target), _ptr(conv_w), _ptr(dO), sp, dp,
-                                    *[_ptr(g) for g in grads], _ptr(ws), nbytes, _stream(dev)),
-           "ttt_layer_backward")
+    name = "ttt_layer_backward_mse" if mode == "mse" else "ttt_layer_backward"
+    _check(getattr(lib(), name)(ctypes.byref(shape), _dt(dt), float(eta), _ptr(H), _ptr(X0), _ptr(W_gate),
+                                _ptr(W_up), _ptr(W_down0), _ptr(W_target), _ptr(conv_w), _ptr(dO), sp, dp,
+                                *[_ptr(g) for g in grads], _ptr(ws), nbytes, _stream(dev)), name)
     return grads
 
 

@@ -510,21 +510,26 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
 // dV^, G = [dA | dU], dY, the two token-contraction scans' scratch (sized for
 // the larger state, [2f, d] or [d, d]), and the tap-gradient partials.
 struct LayerBwdPlan {
-  BwdPlan core;
+  int mode;                     // TTT_MODE_DOT or TTT_MODE_MSE: the chunk loop differentiated
+  BwdPlan core;                 // its backward, dot objective
+  MsePlan mcore;                // its backward, MSE objective
   int64_t B, n, d, f, C, K;
   size_t esz;
   int kk;                       // chunks the weight-gradient scans are cut into (their segments divide it)
   int S_gu, S_t;                // segments of the [dW_gate; dW_up] and dW_target scans
   int64_t DFm, npart;
-  size_t off_Z, off_Y, off_WtT, off_dZ, off_dV, off_G, off_dY, off_wWc, off_wWp, off_wTot, off_wWf, off_wzero,
-      off_part, off_core, total;
+  size_t off_Z, off_Y, off_WtT, off_V, off_dZ, off_dV, off_G, off_dY, off_wWc, off_wWp, off_wTot, off_wWf,
+      off_wzero, off_part, off_core, total;
 };
 
-int make_layer_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, LayerBwdPlan* p) {
+int make_layer_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, LayerBwdPlan* p,
+                        int mode = TTT_MODE_DOT) {
   *p = LayerBwdPlan{};
+  p->mode = mode;
   int st = make_bwd_plan(s, dtype, saved, &p->core, true);
   if (st != TTT_OK) return st;
   if (!p->core.fused) return TTT_ERR_UNSUPPORTED;     // the weight gradients take the fused scan's token steps
+  if (mode == TTT_MODE_MSE && (st = make_mse_plan(s, dtype, &p->mcore, saved)) != TTT_OK) return st;
   p->B = s->batch;
   p->n = s->seq_len;
   p->d = s->d_model;
@@ -550,6 +555,7 @@ int make_layer_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, Layer
   take(&p->off_Z, BN * p->f * e);
   take(&p->off_Y, BN * p->d * e);
   take(&p->off_WtT, (size_t)p->d * p->d * e);
+  if (mode == TTT_MODE_MSE) take(&p->off_V, BN * p->d * e);      // V^ itself (the dot core keeps eta V^)
   take(&p->off_dZ, BN * p->f * e);
   take(&p->off_dV, BN * p->d * e);
   take(&p->off_G, BN * 2 * p->f * e);
@@ -562,7 +568,7 @@ int make_layer_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, Layer
   take(&p->off_wWf, B * DFm * 4);
   take(&p->off_wzero, DFm * e);
   take(&p->off_part, (size_t)p->npart * p->d * p->K * 4);
-  take(&p->off_core, p->core.total);
+  take(&p->off_core, mode == TTT_MODE_MSE ? p->mcore.total : p->core.total);
   p->total = off;
   return TTT_OK;
 }
@@ -607,16 +613,21 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
   float* wWf = (float*)(ws + L.off_wWf);
   float* part = (float*)(ws + L.off_part);
   char* cws = ws + L.off_core;
-  T* Vs = (T*)(cws + L.core.off_Vs);
-  // the forward's activations: Z (eq. (2)), Y = Conv1D(X0), eta V^ = eta Y W_target (eq. (5))
+  const bool mse = L.mode == TTT_MODE_MSE;
+  const uint8_t* docs = mse ? L.mcore.docs : L.core.docs;
+  // the target as the chunk loop's backward takes it: eta V^ in the dot core's own buffer, V^ for MSE
+  T* Vs = mse ? (T*)(ws + L.off_V) : (T*)(cws + L.core.off_Vs);
+  // the forward's activations: Z (eq. (2)), Y = Conv1D(X0), V^ = Y W_target (eq. (5))
   int st = dev(ttt::launch_zero<T>((T*)(ws + L.off_wzero), L.DFm, s));
   if (st == TTT_OK) st = dev(ttt::launch_produce_z<T>(H, Wg, Wu, Z, nullptr, rows, n, d, f, s));
   if (st == TTT_OK)
-    st = dev(ttt::launch_conv<T>((const T*)X0v, (const T*)cwv, Y, rows, n, d, K, L.core.docs, C, false, nullptr, s));
+    st = dev(ttt::launch_conv<T>((const T*)X0v, (const T*)cwv, Y, rows, n, d, K, docs, C, false, nullptr, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Wt, WtT, 1, d, d, 1.0f, 0, s));
-  if (st == TTT_OK) st = dev(ttt::launch_apply<T>(Y, WtT, 0, 0, Vs, B, n, d, d, C, eta, s, true));
+  if (st == TTT_OK) st = dev(ttt::launch_apply<T>(Y, WtT, 0, 0, Vs, B, n, d, d, C, mse ? 1.0f : eta, s, true));
   // the chunk loop: dZ, dV^ and dW_down0
-  if (st == TTT_OK) st = core_backward<T>(L.core, eta, Z, nullptr, W0, dO, Wsaved, dZ, dV, dW0, cws, s, true);
+  if (st == TTT_OK)
+    st = mse ? mse_backward<T>(L.mcore, eta, Z, Vs, W0, dO, Wsaved, dZ, dV, dW0, cws, s)
+             : core_backward<T>(L.core, eta, Z, nullptr, W0, dO, Wsaved, dZ, dV, dW0, cws, s, true);
   // the producer: [dA | dU], then [dW_gate; dW_up] = sum G^T H and dH = dA W_gate + dU W_up
   if (st == TTT_OK) st = dev(ttt::launch_produce_z_bwd<T>(H, Wg, Wu, dZ, G, rows, n, d, f, s));
   if (st == TTT_OK) st = token_contraction<T>(L, H, G, 2 * f, d, L.S_gu, ws, s);
@@ -629,8 +640,7 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
   if (st == TTT_OK) st = dev(ttt::launch_sum_rows(wWf, dWt, B, (int64_t)d * d, s));
   if (st == TTT_OK) st = dev(ttt::launch_apply<T>(dV, Wt, 0, 0, dY, B, n, d, d, C, 1.0f, s, true));
   if (st == TTT_OK)
-    st = dev(ttt::launch_conv_bwd<T>((const T*)X0v, (const T*)cwv, dY, (T*)dX0v, part, rows, n, d, K, s,
-                                     L.core.docs, C));
+    st = dev(ttt::launch_conv_bwd<T>((const T*)X0v, (const T*)cwv, dY, (T*)dX0v, part, rows, n, d, K, s, docs, C));
   if (st == TTT_OK) st = dev(ttt::launch_sum_rows(part, dcw, (int)L.npart, (int64_t)d * K, s));
   return st;
 }
@@ -865,15 +875,31 @@ int ttt_layer_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype
   return TTT_OK;
 }
 
-int ttt_layer_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
-                       const void* W_gate, const void* W_up, const void* W_down0, const void* W_target,
-                       const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
-                       void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
-                       float* dconv_w, void* workspace, size_t workspace_bytes, void* stream) {
+int ttt_layer_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states,
+                                           size_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_ARG;
   LayerBwdPlan p;
-  int st = make_layer_bwd_plan(shape, dtype, W_states != nullptr, &p);
+  int st = make_layer_bwd_plan(shape, dtype, saved_states != 0, &p, TTT_MODE_MSE);
+  if (st != TTT_OK) return st;
+  *bytes = p.total;
+  return TTT_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// The whole layer's backward for either objective (the entry points below).
+int layer_backward_call(int mode, const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
+                        const void* W_gate, const void* W_up, const void* W_down0, const void* W_target,
+                        const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
+                        void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
+                        float* dconv_w, void* workspace, size_t workspace_bytes, void* stream) {
+  LayerBwdPlan p;
+  int st = make_layer_bwd_plan(shape, dtype, W_states != nullptr, &p, mode);
   if (st != TTT_OK) return st;
   p.core.docs = doc_starts;
+  p.mcore.docs = doc_starts;
   if (!finite(eta)) return TTT_ERR_ARG;
   if (!ok_ptr(dW_gate) || !ok_ptr(dW_up) || !ok_ptr(dW_down0) || !ok_ptr(dW_target) || !ok_ptr(dconv_w) ||
       (W_states != nullptr && !aligned16(W_states)))
@@ -890,6 +916,30 @@ int ttt_layer_backward(const ttt_inplace_shape* shape, int dtype, float eta, con
                                 dW_gate, dW_up, dW_down0, dW_target, dconv_w, ws, s);
   return layer_backward<float>(p, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, W_states, dH, dX0,
                                dW_gate, dW_up, dW_down0, dW_target, dconv_w, ws, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_layer_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
+                       const void* W_gate, const void* W_up, const void* W_down0, const void* W_target,
+                       const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
+                       void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
+                       float* dconv_w, void* workspace, size_t workspace_bytes, void* stream) {
+  return layer_backward_call(TTT_MODE_DOT, shape, dtype, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO,
+                             W_states, doc_starts, dH, dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w, workspace,
+                             workspace_bytes, stream);
+}
+
+int ttt_layer_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
+                           const void* W_gate, const void* W_up, const void* W_down0, const void* W_target,
+                           const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
+                           void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
+                           float* dconv_w, void* workspace, size_t workspace_bytes, void* stream) {
+  return layer_backward_call(TTT_MODE_MSE, shape, dtype, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO,
+                             W_states, doc_starts, dH, dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w, workspace,
+                             workspace_bytes, stream);
 }
 
 int ttt_produce_z(const ttt_inplace_shape* shape, int dtype, const void* H, const void* W_gate, const void* W_up,

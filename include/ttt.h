@@ -350,6 +350,30 @@ int ttt_layer_backward(const ttt_inplace_shape* shape, int dtype, float eta, con
                        void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
                        float* dconv_w, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- backward of the whole MSE layer ---- */
+
+/* Workspace bytes for ttt_layer_backward_mse (saved_states as for
+ * ttt_core_backward_mse_workspace_bytes): the layer backward's own buffers
+ * (as for ttt_layer_backward_workspace_bytes, plus V^ [B, n, d] dtype) beside
+ * the MSE chunk loop's (ttt_core_backward_mse_workspace_bytes). */
+int ttt_layer_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states,
+                                           size_t* bytes);
+
+/* ttt_layer_backward for the MSE objective (ttt_chunk_apply_update with
+ * TTT_MODE_MSE and the causal convolution; In-Place TTT review, Method §1-§3,
+ * eq. (1)-(5), the update of eq. (4) on the squared error (1/(2C))||Z_c W^T -
+ * V^_c||^2): the same arguments, outputs, rules and errors.  The chunk loop's
+ * gradients dZ, dV^ and dW_down0 come from the reverse recursion of
+ * ttt_core_backward_mse (its states W_states [B, k, d, f] dtype when the
+ * forward MSE call kept them, else recomputed); the producers', the target's
+ * and the convolution's gradients follow as for the dot layer.  With packed
+ * documents each is differentiated as an independent sequence. */
+int ttt_layer_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
+                           const void* W_gate, const void* W_up, const void* W_down0, const void* W_target,
+                           const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
+                           void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
+                           float* dconv_w, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- the individual steps (each is one stage of the call above; they compose
  *      into it and exist for composition and per-step checks).  The updates
  *      contract over tokens, so they read token-contiguous (transposed) copies:

@@ -366,3 +366,86 @@ def test_mse_backward_packed_documents(dtype, C):
         for name, a, b in zip(("dZ", "dVhat", "dW_down0"), res, ref):
             assert rel(f64(a), b) < TOL[dtype], name
     assert not torch.any(got[1][1])       # a document per chunk: no later state in any document
+
+
+# ---------------------------------------------------------------- the whole MSE layer
+
+def mse_layer_case(dtype, B, n, C, K=4, d=264, f=392, eta=0.5, seed=61):
+    cfg = ti.InplaceConfig("mlbwd", B, n, d, f, C, eta, "mse", dtype, conv_k=K, seed=seed)
+    x = ti.inplace_inputs(cfg)
+    dO = ti.backward_inputs(cfg.with_(seed=seed + 1))["dO"]
+    return cfg, x, dO
+
+
+def mse_layer_ref(cfg, x, dO, doc_starts=None):
+    return orc.layer_backward(*(ti.to_f64(x[name]) for name in ("H", "X0", "W_gate", "W_up", "W_down0", "W_target",
+                                                                "conv_w")), cfg.chunk, cfg.eta, ti.to_f64(dO),
+                              doc_starts=doc_starts, mode="mse")
+
+
+@pytest.mark.parametrize("dtype,C,k,K", [("f32", 96, 3, 4), ("bf16", 128, 4, 4), ("bf16", 64, 3, 1),
+                                         ("f32", 64, 4, 3)])
+def test_mse_layer_backward_matches_oracle(dtype, C, k, K):
+    """Every gradient of the whole MSE-objective layer (ttt_layer_backward_mse) against the oracle, two rows sharing
+    the weights, ragged 256-tiles in d and f."""
+    cfg, x, dO = mse_layer_case(dtype, 2, k * C, C, K)
+    g = {name: t.cuda() for name, t in x.items()}
+    grads = cw.ttt_layer_backward_mse(*layer_args(g), dO.cuda(), C, cfg.eta)
+    torch.cuda.synchronize()
+    for name, got, want in zip(GRAD_NAMES, grads, mse_layer_ref(cfg, x, dO)):
+        assert rel(f64(got), want) < TOL[dtype], name
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mse_layer_backward_packed_documents_and_kept_states(dtype):
+    """Packed documents (row 0: documents of 2, 3 and 1 chunks; row 1: 1, 2 and 3) with the states recomputed and
+    with the states the MSE forward layer kept under the same document starts."""
+    cfg, x, dO = mse_layer_case(dtype, 2, 6 * 128, 128)
+    starts = np.array([[1, 0, 1, 0, 0, 1], [1, 1, 0, 1, 0, 0]], dtype=np.uint8)
+    dst = torch.from_numpy(starts).cuda()
+    g = {name: t.cuda() for name, t in x.items()}
+    got = cw.ttt_layer_backward_mse(*layer_args(g), dO.cuda(), cfg.chunk, cfg.eta, doc_starts=dst)
+    Ws = torch.empty(2, 6, cfg.d_model, cfg.d_ff, dtype=g["H"].dtype, device="cuda")
+    cw.ttt_chunk_apply_update(*layer_args(g), cfg.chunk, cfg.eta, "mse", W_states=Ws, doc_starts=dst)
+    kept = cw.ttt_layer_backward_mse(*layer_args(g), dO.cuda(), cfg.chunk, cfg.eta, doc_starts=dst, W_states=Ws)
+    torch.cuda.synchronize()
+    ref = mse_layer_ref(cfg, x, dO, doc_starts=starts)
+    for res in (got, kept):
+        for name, a, want in zip(GRAD_NAMES, res, ref):
+            assert rel(f64(a), want) < TOL[dtype], name
+
+
+def test_mse_layer_backward_single_chunk_empty_and_unsupported():
+    # one chunk: the targets reach no output, so dX0, dW_target and the taps' gradient are exactly zero
+    cfg, x, dO = mse_layer_case("bf16", 2, 256, 256)
+    g = {name: t.cuda() for name, t in x.items()}
+    grads = cw.ttt_layer_backward_mse(*layer_args(g), dO.cuda(), cfg.chunk, cfg.eta)
+    torch.cuda.synchronize()
+    assert not torch.any(grads[1]) and not torch.any(grads[5]) and not torch.any(grads[6])
+    ref = mse_layer_ref(cfg, x, dO)
+    for i in (0, 2, 3, 4):
+        assert rel(f64(grads[i]), ref[i]) < TOL["bf16"], GRAD_NAMES[i]
+    for B, n in ((0, 256), (2, 0)):
+        cfg, x, dO = mse_layer_case("f32", B, n, 128)
+        g = {name: t.cuda() for name, t in x.items()}
+        grads = cw.ttt_layer_backward_mse(*layer_args(g), dO.cuda(), 128, 0.5)
+        torch.cuda.synchronize()
+        assert all(not torch.any(t) for t in grads[2:])
+    cfg, x, dO = mse_layer_case("bf16", 1, 240, 80)
+    g = {name: t.cuda() for name, t in x.items()}
+    with pytest.raises(cw.TTTError) as e:
+        cw.ttt_layer_backward_mse(*layer_args(g), dO.cuda(), 80, 0.5)
+    assert e.value.status == cw.TTT_ERR_UNSUPPORTED
+
+
+def test_mse_layer_backward_reduced_workload():
+    """The MSE workload's rows, conv width and eta at a size the oracle finishes in seconds: 4 rows of 4096 tokens,
+    d 512, d_ff 2048, chunk 512 (8 chunks)."""
+    cfg = ti.workload("mse_bf16_4x64k").with_(seq_len=4096, d_model=512, d_ff=2048, chunk=512)
+    x = ti.inplace_inputs(cfg)
+    dO = ti.backward_inputs(cfg.with_(seed=cfg.seed + 3, backward=True))["dO"]
+    g = {name: t.cuda() for name, t in x.items()}
+    grads = cw.ttt_layer_backward_mse(*layer_args(g), dO.cuda(), cfg.chunk, cfg.eta)
+    torch.cuda.synchronize()
+    for name, got, want in zip(GRAD_NAMES, grads, mse_layer_ref(cfg, x, dO)):
+        assert rel(f64(got), want) < TOL["bf16"], name

@@ -91,10 +91,13 @@ class InplaceConfig:
         update 2df, apply 2df per token.  Backward of the chunk loop: 10df per
         token (the states' scan, the suffixes' scan, dVhat, and dZ's two
         contractions, 2df each); 8df with the states kept by the forward call.
-        Backward of the whole layer: that, plus the producer's recompute and
-        its backward (4df each), the gate and up weight gradients (4df), dH
-        (4df), and eta V^, dW_target and dY (2d^2 each)."""
+        Backward of the whole layer: that (or the MSE loop's, below), plus
+        the producer's recompute and its backward (4df each), the gate and
+        up weight gradients (4df), dH (4df), and V^, dW_target and dY (2d^2
+        each)."""
         d, f, K = self.d_model, self.d_ff, self.conv_k
+        if self.layer_backward and self.mode == "mse":
+            return float(self.tokens) * ((26.0 if self.kept_states else 30.0) * d * f + 6.0 * d * d)
         if self.layer_backward:
             return float(self.tokens) * ((24.0 if self.kept_states else 26.0) * d * f + 6.0 * d * d)
         if self.backward and self.mode == "mse":
@@ -197,6 +200,11 @@ WORKLOADS = {
     "mse_bwd_bf16_4x64k_kept": InplaceConfig("mse_bwd_bf16_4x64k_kept", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16",
                                              seed=1006, backward=True, kept_states=True),
     "mse_bf16_4x64k": InplaceConfig("mse_bf16_4x64k", 4, 65536, 2048, 8192, 2048, 1.0, "mse", "bf16", seed=1003),
+    # the backward of the whole MSE-objective layer at the MSE workload's shape (states recomputed, or kept)
+    "mse_layer_bwd_bf16_4x64k": InplaceConfig("mse_layer_bwd_bf16_4x64k", 4, 65536, 2048, 8192, 2048, 1.0, "mse",
+                                              "bf16", seed=1003, layer_backward=True),
+    "mse_layer_bwd_bf16_4x64k_kept": InplaceConfig("mse_layer_bwd_bf16_4x64k_kept", 4, 65536, 2048, 8192, 2048, 1.0,
+                                                   "mse", "bf16", seed=1003, layer_backward=True, kept_states=True),
     "lact_bf16_256k": LactConfig("lact_bf16_256k", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004),
     # the LaCT review's own update: dot-product loss, per-token learning rates, L2 weight normalisation
     "lact_bf16_256k_paper": LactConfig("lact_bf16_256k_paper", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
