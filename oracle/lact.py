@@ -37,7 +37,8 @@ import numpy as np
 
 from .inplace import silu
 
-__all__ = ["swiglu_apply", "swiglu_loss", "swiglu_grads", "muon", "l2_normalize_rows", "lact_layer"]
+__all__ = ["swiglu_apply", "swiglu_loss", "swiglu_grads", "muon", "l2_normalize_rows", "lact_layer",
+           "lact_backward"]
 
 
 def _f64(a):
@@ -158,3 +159,124 @@ def lact_layer(q, k, v, W1, W3, W2, chunk, eta, order="update_then_apply", updat
                     raise ValueError(f"unknown order {order!r}")
             W1f[b, h], W3f[b, h], W2f[b, h] = w1, w3, w2
     return O, W1f, W3f, W2f
+
+
+def _sigmoid(x):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def _apply_backward(x, W1, W3, W2, dO):
+    """Backward of o = f_W(x) (eq. (4)) for a chunk of rows x [C, dh] given
+    dO [C, dh]: returns (dx [C, dh], dW1 [m, dh], dW3 [m, dh], dW2 [dh, m])."""
+    A = x @ W1.T
+    U = x @ W3.T
+    sg = _sigmoid(A)
+    S = A * sg                                 # silu(A)
+    Hq = S * U
+    dW2 = dO.T @ Hq
+    dH = dO @ W2
+    dA = dH * U * (sg * (1.0 + A * (1.0 - sg)))   # silu'(A)
+    dU = dH * S
+    return dA @ W1 + dU @ W3, dA.T @ x, dU.T @ x, dW2
+
+
+def _update_backward(kc, vc, W1, W3, W2, gG1, gG3, gG2):
+    """Backward of the chunk gradient (G1, G3, G2) = swiglu_grads(kc, vc, W)
+    (the squared error summed over the chunk) given upstream gradients
+    (gG1, gG3, gG2) of the same shapes: returns (dk [C, dh], dv [C, dh],
+    dW1, dW3, dW2), the second-order terms through W included.  The forward
+    it differentiates, in the order written in swiglu_grads:
+      A = k W1^T, U = k W3^T, S = silu(A), Hh = S U, Y = Hh W2^T, R = Y - v,
+      dH = R W2, dU = dH S, dA = dH U silu'(A),
+      G2 = R^T Hh, G3 = dU^T k, G1 = dA^T k,
+    with silu'(a) = s(a)(1 + a(1 - s(a))) and
+    silu''(a) = s(a)(1 - s(a))(2 + a(1 - 2 s(a))), s the logistic function."""
+    A = kc @ W1.T
+    U = kc @ W3.T
+    sg = _sigmoid(A)
+    S = A * sg
+    s1 = sg * (1.0 + A * (1.0 - sg))
+    s2 = sg * (1.0 - sg) * (2.0 + A * (1.0 - 2.0 * sg))
+    Hh = S * U
+    R = Hh @ W2.T - vc
+    dH = R @ W2
+    dU = dH * S
+    dA = dH * U * s1
+    # G1 = dA^T k, G3 = dU^T k, G2 = R^T Hh
+    ddA = kc @ gG1.T
+    ddU = kc @ gG3.T
+    dk = dA @ gG1 + dU @ gG3
+    dR = Hh @ gG2.T
+    dHh = R @ gG2
+    # dA = dH U silu'(A); dU = dH S
+    ddH = ddA * U * s1 + ddU * S
+    dU_f = ddA * dH * s1
+    dA_f = ddA * dH * U * s2
+    dS = ddU * dH
+    # dH = R W2
+    dR = dR + ddH @ W2.T
+    dW2 = R.T @ ddH
+    # R = Y - v, Y = Hh W2^T
+    dv = -dR
+    dHh = dHh + dR @ W2
+    dW2 = dW2 + dR.T @ Hh
+    # Hh = S U, S = silu(A)
+    dS = dS + dHh * U
+    dU_f = dU_f + dHh * S
+    dA_f = dA_f + dS * s1
+    # A = k W1^T, U = k W3^T
+    dk = dk + dA_f @ W1 + dU_f @ W3
+    return dk, dv, dA_f.T @ kc, dU_f.T @ kc, dW2
+
+
+def lact_backward(q, k, v, W1, W3, W2, chunk, eta, dO, order="update_then_apply"):
+    """Gradients of a loss that depends on the output O of lact_layer (the
+    squared error, plain GD, no mask or other variant) with respect to every
+    input, given dO = dLoss/dO [B, H, n, dh]: returns (dq, dk, dv
+    [B, H, n, dh], dW1, dW3 [H, m, dh], dW2 [H, dh, m]); the initial weights
+    are shared by the batch rows, so their gradients add over rows.
+
+    The chain rule through the chunk loop (LaCT Model Architecture §1, eq.
+    (3)-(4)), from the last chunk back.  With W_c the state chunk c's update
+    starts from and W_{c+1} = W_c - eta G(W_c; k_c, v_c), let gW be the
+    gradient with respect to the state after chunk c (zero after the last
+    chunk).  Chunk c's queries are applied with W_{c+1} (update-then-apply) or
+    W_c (apply-then-update): that apply's backward (_apply_backward) gives dq_c
+    and adds its weight gradients to gW or to the result.  The update gives
+    dLoss/dW_c = gW + (terms of G's backward with upstream -eta gW)
+    (_update_backward), and dk_c, dv_c from the same backward."""
+    q, k, v, dO = map(_f64, (q, k, v, dO))
+    W1, W3, W2 = _f64(W1), _f64(W3), _f64(W2)
+    B, Hn, n, dh = q.shape
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    dW1, dW3, dW2 = np.zeros_like(W1), np.zeros_like(W3), np.zeros_like(W2)
+    bounds = [(s, min(s + chunk, n)) for s in range(0, n, chunk)]
+    if order not in ("update_then_apply", "apply_then_update"):
+        raise ValueError(f"unknown order {order!r}")
+    for b in range(B):
+        for h in range(Hn):
+            states = []                          # the state each chunk's update starts from
+            w = (W1[h].copy(), W3[h].copy(), W2[h].copy())
+            for s, e in bounds:
+                states.append(w)
+                g1, g3, g2 = swiglu_grads(k[b, h, s:e], v[b, h, s:e], *w)
+                w = (w[0] - eta * g1, w[1] - eta * g3, w[2] - eta * g2)
+            states.append(w)
+            g = [np.zeros_like(W1[h]), np.zeros_like(W3[h]), np.zeros_like(W2[h])]   # gradient after the last chunk
+            for c in range(len(bounds) - 1, -1, -1):
+                s, e = bounds[c]
+                if order == "update_then_apply":       # the queries see the updated state
+                    dqc, a1, a3, a2 = _apply_backward(q[b, h, s:e], *states[c + 1], dO[b, h, s:e])
+                    g = [g[0] + a1, g[1] + a3, g[2] + a2]
+                dkc, dvc, u1, u3, u2 = _update_backward(k[b, h, s:e], v[b, h, s:e], *states[c],
+                                                        -eta * g[0], -eta * g[1], -eta * g[2])
+                g = [g[0] + u1, g[1] + u3, g[2] + u2]
+                if order == "apply_then_update":       # the queries see the state before the update
+                    dqc, a1, a3, a2 = _apply_backward(q[b, h, s:e], *states[c], dO[b, h, s:e])
+                    g = [g[0] + a1, g[1] + a3, g[2] + a2]
+                dq[b, h, s:e], dk[b, h, s:e], dv[b, h, s:e] = dqc, dkc, dvc
+            dW1[h] += g[0]
+            dW3[h] += g[1]
+            dW2[h] += g[2]
+    return dq, dk, dv, dW1, dW3, dW2

@@ -288,3 +288,80 @@ def test_muon_update_in_the_layer():
         np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-13)
     ref = _torch_swiglu(*(torch.from_numpy(a) for a in (q[0, 0], n1, n3, n2))).numpy()
     np.testing.assert_allclose(O[0, 0], ref, rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------- backward of the layer
+
+def _torch_lact_layer(q, k, v, W1, W3, W2, chunk, eta, order):
+    """The LaCT layer in torch float64 with the inner gradient taken by autograd itself (create_graph, so that an
+    outer backward differentiates through it), for the backward's pin."""
+    B, Hn, n, dh = q.shape
+    rows = []
+    for b in range(B):
+        heads = []
+        for h in range(Hn):
+            w = [W1[h], W3[h], W2[h]]
+            outs = []
+            for s in range(0, n, chunk):
+                qc, kc, vc = q[b, h, s:s + chunk], k[b, h, s:s + chunk], v[b, h, s:s + chunk]
+                if order == "apply_then_update":
+                    outs.append(_torch_swiglu(qc, *w))
+                loss = 0.5 * ((_torch_swiglu(kc, *w) - vc) ** 2).sum()
+                grads = torch.autograd.grad(loss, w, create_graph=True)
+                w = [wi - eta * gi for wi, gi in zip(w, grads)]
+                if order == "update_then_apply":
+                    outs.append(_torch_swiglu(qc, *w))
+            heads.append(torch.cat(outs))
+        rows.append(torch.stack(heads))
+    return torch.stack(rows)
+
+
+@pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
+@pytest.mark.parametrize("n,chunk", [(12, 4), (10, 4), (6, 6)])
+def test_lact_backward_matches_autograd(order, n, chunk):
+    """Every gradient of the layer (q, k, v and the three initial weights, shared by two batch rows) against torch
+    autograd of the layer whose inner chunk gradient autograd also takes (second-order terms through the update
+    included); a ragged last chunk and a single chunk."""
+    q, k, v, W1, W3, W2 = _problem(70, B=2, H=2, n=n, dh=3, m=5)
+    eta = 0.7
+    dO = np.random.default_rng(71).standard_normal(q.shape)
+    ours = orc.lact_backward(q, k, v, W1, W3, W2, chunk, eta, dO, order)
+    ts = [torch.tensor(a, requires_grad=True) for a in (q, k, v, W1, W3, W2)]
+    out = _torch_lact_layer(*ts, chunk, eta, order)
+    (out * torch.from_numpy(dO)).sum().backward()
+    for got, t in zip(ours, ts):
+        # (one chunk applied before its update: k and v reach no output, autograd gives no gradient)
+        want = np.zeros(t.shape) if t.grad is None else t.grad.numpy()
+        np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+    # the forward it differentiates is the oracle's layer
+    O, *_ = orc.lact_layer(q, k, v, W1, W3, W2, chunk, eta, order)
+    np.testing.assert_allclose(O, out.detach().numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_lact_backward_finite_differences_and_eta_zero():
+    """Central differences of <O, dO> through the oracle's layer for entries of q, k, v and each initial weight;
+    with eta = 0 the layer is the plain SwiGLU on the queries: dk = dv = 0 and the weight gradients are the
+    apply's alone."""
+    q, k, v, W1, W3, W2 = _problem(72, B=1, H=1, n=8, dh=3, m=4)
+    eta, chunk = 0.6, 4
+    dO = np.random.default_rng(73).standard_normal(q.shape)
+    grads = orc.lact_backward(q, k, v, W1, W3, W2, chunk, eta, dO)
+    args = [q, k, v, W1, W3, W2]
+    L = lambda a: float(np.sum(orc.lact_layer(*a, chunk, eta)[0] * dO))
+    h = 1e-6
+    for which, idx in ((0, (0, 0, 5, 1)), (1, (0, 0, 2, 0)), (1, (0, 0, 6, 2)), (2, (0, 0, 1, 1)), (3, (0, 2, 1)),
+                       (4, (0, 1, 0)), (5, (0, 2, 3))):
+        p = [a.copy() for a in args]
+        m = [a.copy() for a in args]
+        p[which][idx] += h
+        m[which][idx] -= h
+        g = grads[which][idx]
+        assert abs((L(p) - L(m)) / (2 * h) - g) < 1e-6 * max(1.0, abs(g)), (which, idx)
+    dq, dk, dv, dW1, dW3, dW2 = orc.lact_backward(q, k, v, W1, W3, W2, chunk, 0.0, dO)
+    assert not dk.any() and not dv.any()
+    qt = torch.tensor(q[0, 0], requires_grad=True)
+    ws = [torch.tensor(a[0], requires_grad=True) for a in (W1, W3, W2)]
+    (_torch_swiglu(qt, *ws) * torch.from_numpy(dO[0, 0])).sum().backward()
+    np.testing.assert_allclose(dq[0, 0], qt.grad.numpy(), rtol=1e-12, atol=1e-13)
+    for got, t in zip((dW1[0], dW3[0], dW2[0]), ws):
+        np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-12, atol=1e-13)
