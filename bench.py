@@ -167,7 +167,7 @@ def bench_generic(cfg, steps, warmup):
         ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
         call = lambda: cw.ttt_layer_backward(*w, dO, cfg.chunk, cfg.eta, W_states=Ws, grads=grads, workspace=ws,
                                              mode=cfg.mode)
-    elif getattr(cfg, "backward", False):
+    elif getattr(cfg, "backward", False) and not isinstance(cfg, ti.LactConfig):
         x = ti.backward_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
         B, n, d, f = cfg.batch, cfg.seq_len, cfg.d_model, cfg.d_ff
@@ -199,6 +199,19 @@ def bench_generic(cfg, steps, warmup):
             ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
             call = lambda: cw.ttt_core_backward(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta, dZ, dV,
                                                 dW0, ws, W_states=Ws)
+    elif isinstance(cfg, ti.LactConfig) and cfg.backward:
+        x = ti.lact_inputs(cfg)
+        g = {k: v.cuda() for k, v in x.items()}
+        dO = lact_upstream(cfg, x).cuda()
+        B, Hh, n, dh, m = cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.hidden
+        dt = g["q"].dtype
+        grads = tuple(torch.empty(*shp, dtype=t, device="cuda") for shp, t in (
+            ((B, Hh, n, dh), dt), ((B, Hh, n, dh), dt), ((B, Hh, n, dh), dt), ((Hh, m, dh), torch.float32),
+            ((Hh, m, dh), torch.float32), ((Hh, dh, m), torch.float32)))
+        nbytes = cw.ttt_lact_backward_workspace_bytes(cw.LactShape(B, Hh, n, dh, m, cfg.chunk), dt)
+        ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
+        call = lambda: cw.ttt_lact_swiglu_backward(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], dO, cfg.chunk,
+                                                   cfg.eta, cfg.order, grads=grads, workspace=ws)
     elif isinstance(cfg, ti.LactConfig):
         x = ti.lact_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
@@ -241,6 +254,13 @@ def bench_generic(cfg, steps, warmup):
     return wall, {"layer": e0.elapsed_time(e1) / steps}
 
 
+def lact_upstream(cfg, x):
+    """The upstream gradient dLoss/dO of the LaCT backward: standard normal, seeded after the layer's inputs."""
+    import torch
+    gen = torch.Generator().manual_seed(cfg.seed + 7)
+    return torch.randn(*x["q"].shape, generator=gen).to(x["q"].dtype)
+
+
 def cpu_baseline(cfg, target_s):
     """The float64 oracle on whole leading chunks of the same workload."""
     import numpy as np
@@ -253,7 +273,14 @@ def cpu_baseline(cfg, target_s):
     # the host cores this process may run on, with the BLAS pool sized to match
     cores = len(os.sched_getaffinity(0))
     threadpoolctl.threadpool_limits(limits=cores)
-    if isinstance(cfg, ti.LactConfig):
+    if isinstance(cfg, ti.LactConfig) and cfg.backward:
+        x = ti.lact_inputs(cfg)
+        dO = lact_upstream(cfg, x)
+        run = lambda kc: olact.lact_backward(*(ti.to_f64(x[k][:, :1, : kc * cfg.chunk]) if k in "qkv"
+                                               else ti.to_f64(x[k][:1]) for k in ("q", "k", "v", "W1", "W3", "W2")),
+                                             cfg.chunk, cfg.eta, ti.to_f64(dO[:, :1, : kc * cfg.chunk]), cfg.order)
+        per_tok_heads = 1
+    elif isinstance(cfg, ti.LactConfig):
         x = ti.lact_inputs(cfg)
         umask = cfg.update_mask()
         run = lambda kc: olact.lact_layer(*(ti.to_f64(x[k][:, :1, : kc * cfg.chunk]) if k in "qkv"
@@ -348,6 +375,9 @@ def main():
         if cfg.loss != "mse" or cfg.weight_norm or cfg.token_rates or cfg.muon:
             out["config"].update({"loss": cfg.loss, "weight_norm": cfg.weight_norm, "token_rates": cfg.token_rates,
                                   "muon": cfg.muon})
+        if cfg.backward:
+            out["config"]["pass"] = "backward of the LaCT layer (dq, dk, dv and the initial weights' gradients)"
+            out["metric"] = "LaCT-layer backward tokens/s at 256K ctx; % of bf16 MFMA peak"
     else:
         out["config"] = {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_len, "d_model": cfg.d_model,
                          "d_ff": cfg.d_ff, "chunk": cfg.chunk, "conv_k": cfg.conv_k, "eta": cfg.eta,
@@ -366,7 +396,8 @@ def main():
         if cfg.layer_backward:
             out["config"]["pass"] = "backward of the whole layer (every input and weight gradient from dLoss/dO)"
             out["config"]["states"] = "kept by the forward call" if cfg.kept_states else "recomputed"
-            out["metric"] = "TTT-layer backward tokens/s at 128K ctx; % of bf16 MFMA peak"
+            out["metric"] = ("TTT-layer backward tokens/s at " + ("4x64K" if cfg.mode == "mse" else "128K") +
+                             " ctx; % of bf16 MFMA peak")
 
     if (not isinstance(cfg, ti.LactConfig) and cfg.mode == "dot" and cfg.docs == 1 and not cfg.conv_forward and
             cfg.pieces == 1 and not cfg.backward and not cfg.layer_backward):

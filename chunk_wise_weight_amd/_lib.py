@@ -108,6 +108,8 @@ _SIGNATURES = {
                              _S, _P]),
     "ttt_lact_swiglu_ex": (_I, [ctypes.POINTER(LactShape), _I, _F, _P, _P, _P, _P, _P, _P,
                                 ctypes.POINTER(LactOptions), _P, _P, _P, _P, _P, _S, _P]),
+    "ttt_lact_backward_workspace_bytes": (_I, [ctypes.POINTER(LactShape), _I, ctypes.POINTER(_S)]),
+    "ttt_lact_swiglu_backward": (_I, [ctypes.POINTER(LactShape), _I, _I, _F] + [_P] * 13 + [_P, _S, _P]),
 }
 
 _lib = None
@@ -649,3 +651,37 @@ def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_t
                                     _ptr(W2f), _ptr(ws), nbytes, _stream(dev)),
            "ttt_lact_swiglu_ex")
     return O, W1f, W3f, W2f
+
+
+def ttt_lact_backward_workspace_bytes(shape: LactShape, dtype: torch.dtype) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().ttt_lact_backward_workspace_bytes(ctypes.byref(shape), _dt(dtype), ctypes.byref(out)),
+           "ttt_lact_backward_workspace_bytes")
+    return out.value
+
+
+def ttt_lact_swiglu_backward(q, k, v, W1, W3, W2, dO, chunk: int, eta: float, order="update_then_apply",
+                             grads=None, workspace=None):
+    """Backward of the LaCT layer (squared error, plain GD) given dO = dLoss/dO [B, H, n, dh].  Returns (dq, dk,
+    dv [B, H, n, dh] in the inputs' dtype, dW1, dW3 [H, m, dh], dW2 [H, dh, m] fp32, summed over the batch rows)."""
+    B, Hh, n, dh = q.shape
+    m = W1.shape[1]
+    dt, dev = q.dtype, q.device
+    for name, t, shp in (("q", q, (B, Hh, n, dh)), ("k", k, (B, Hh, n, dh)), ("v", v, (B, Hh, n, dh)),
+                         ("W1", W1, (Hh, m, dh)), ("W3", W3, (Hh, m, dh)), ("W2", W2, (Hh, dh, m)),
+                         ("dO", dO, (B, Hh, n, dh))):
+        _need(t, name, shp, dt, dev)
+    shapes = (((B, Hh, n, dh), dt),) * 3 + (((Hh, m, dh), torch.float32), ((Hh, m, dh), torch.float32),
+                                            ((Hh, dh, m), torch.float32))
+    if grads is None:
+        grads = tuple(torch.empty(*shp, dtype=t, device=dev) for shp, t in shapes)
+    for gt, (shp, t) in zip(grads, shapes):
+        _need(gt, "gradient", shp, t, dev)
+    shape = LactShape(B, Hh, n, dh, m, int(chunk))
+    nbytes = ttt_lact_backward_workspace_bytes(shape, dt)
+    ws = _workspace(nbytes, dev, workspace)
+    ordc = _ORDERS[order] if isinstance(order, str) else int(order)
+    _check(lib().ttt_lact_swiglu_backward(ctypes.byref(shape), _dt(dt), ordc, float(eta), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(W1), _ptr(W3), _ptr(W2), _ptr(dO), *[_ptr(g) for g in grads],
+                                          _ptr(ws), nbytes, _stream(dev)), "ttt_lact_swiglu_backward")
+    return grads

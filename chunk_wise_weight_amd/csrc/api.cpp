@@ -1148,6 +1148,49 @@ int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta
                             workspace_bytes, stream);
 }
 
+int ttt_lact_backward_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* bytes) {
+  if (bytes == nullptr) return TTT_ERR_ARG;
+  int st = check_lact(shape, dtype);
+  if (st != TTT_OK) return st;
+  const int B = (int)shape->batch, H = (int)shape->heads, n = (int)shape->seq_len, dh = (int)shape->head_dim,
+            m = (int)shape->hidden, C = (int)shape->chunk;
+  *bytes = dtype == TTT_BF16 ? ttt::lact_bwd_workspace_bytes<bf16>(B, H, n, dh, m, C)
+                             : ttt::lact_bwd_workspace_bytes<float>(B, H, n, dh, m, C);
+  return TTT_OK;
+}
+
+int ttt_lact_swiglu_backward(const ttt_lact_shape* shape, int dtype, int order, float eta, const void* q,
+                             const void* k, const void* v, const void* W1, const void* W3, const void* W2,
+                             const void* dO, void* dq, void* dk, void* dv, float* dW1, float* dW3, float* dW2,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_lact(shape, dtype);
+  if (st != TTT_OK) return st;
+  if (order != TTT_UPDATE_THEN_APPLY && order != TTT_APPLY_THEN_UPDATE) return TTT_ERR_ARG;
+  if (!finite(eta)) return TTT_ERR_ARG;
+  const int B = (int)shape->batch, H = (int)shape->heads, n = (int)shape->seq_len, dh = (int)shape->head_dim,
+            m = (int)shape->hidden, C = (int)shape->chunk;
+  if (H > 0 && (!ok_ptr(W1) || !ok_ptr(W3) || !ok_ptr(W2) || !ok_ptr(dW1) || !ok_ptr(dW3) || !ok_ptr(dW2)))
+    return TTT_ERR_ARG;
+  if ((int64_t)B * H * n > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(dO) || !ok_ptr(dq) ||
+                                 !ok_ptr(dk) || !ok_ptr(dv)))
+    return TTT_ERR_ARG;
+  const size_t need = dtype == TTT_BF16 ? ttt::lact_bwd_workspace_bytes<bf16>(B, H, n, dh, m, C)
+                                        : ttt::lact_bwd_workspace_bytes<float>(B, H, n, dh, m, C);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)) return TTT_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (H == 0) return TTT_OK;
+  if (B == 0) {                    // no row: every weight gradient is zero
+    const int64_t md = (int64_t)m * dh * H;
+    int r = dev(ttt::launch_zero<float>(dW1, md, s));
+    if (r == TTT_OK) r = dev(ttt::launch_zero<float>(dW3, md, s));
+    if (r == TTT_OK) r = dev(ttt::launch_zero<float>(dW2, md, s));
+    return r;
+  }
+  ttt::LactBwdArgs a{B, H, n, dh, m, C, order, eta, q, k, v, W1, W3, W2, dO, dq, dk, dv, dW1, dW3, dW2,
+                     (char*)workspace};
+  return dev(dtype == TTT_BF16 ? ttt::launch_lact_backward<bf16>(a, s) : ttt::launch_lact_backward<float>(a, s));
+}
+
 int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta, const void* q, const void* k, const void* v,
                        const void* W1, const void* W3, const void* W2, const ttt_lact_options* options, void* O,
                        float* W1_f, float* W3_f, float* W2_f, void* workspace, size_t workspace_bytes,

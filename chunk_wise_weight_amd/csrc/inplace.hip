@@ -849,20 +849,6 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
 // Two operands of one tile shape read back to back along K: steps 0 .. n1 - 1
 // from the first, the rest from the second.  They share the LDS layout, so one
 // accumulator takes the sum of both contractions in one stream of K steps.
-template <class OP>
-struct Concat {
-  OP a, b;
-  int n1;
-  static constexpr int kReads = OP::kReads;
-  __device__ static __forceinline__ u32x4 frag(const char* t, int m0, int g) { return OP::frag(t, m0, g); }
-  __device__ __forceinline__ void issue(int ks, char* tile) const {
-    if (ks < n1)
-      a.issue(ks, tile);
-    else
-      b.issue(ks - n1, tile);
-  }
-};
-
 // dZ_j = dO_j W_j + eta V^_j S_j for every chunk j, with W_j the state chunk j
 // was applied with and S_j = sum_{c>j} dO_c^T Z_c (Method §3's prefix form
 // differentiated; see the backward entry point).  P = d_ff columns of the

@@ -622,6 +622,19 @@ __global__ __launch_bounds__(256) void k_lact_init(const T* __restrict__ W1, con
   store4(Ws, x[0], x[1], x[2], x[3]);
 }
 
+// A row group's operand copies (W1, W3, W2) into a kept-state slot [BH, 3, m dh],
+// four elements per thread; grid.y = bh * 3 + w.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lact_keep(const T* __restrict__ W1s, const T* __restrict__ W3s,
+                                                   const T* __restrict__ W2s, T* __restrict__ dst, int64_t md) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= md) return;
+  const int bh = blockIdx.y / 3, w = blockIdx.y % 3;
+  const T* src = (w == 0 ? W1s : (w == 1 ? W3s : W2s)) + (int64_t)bh * md + e;
+  const f32x4 x = load4(src);
+  store4(dst + (int64_t)blockIdx.y * md + e, x[0], x[1], x[2], x[3]);
+}
+
 // ------------------------------------------------------------------ host driver
 
 // The chunk steps of one (batch, head) row are a chain of short launches, each
@@ -691,6 +704,14 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
   if (want()) k_lact_init<T><<<ew, 256, 0, s>>>((const T*)a.W1, (const T*)a.W3, (const T*)a.W2, W1f, W3f, W2f, W1s, W3s, W2s,
                                     bh0, a.H, dh, m);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  // kept states: slot c of row bh at keep + ((c B H + bh0 + bh) 3 + w) m dh
+  auto keep_slot = [&](int c) -> hipError_t {
+    if (a.keep == nullptr) return hipSuccess;
+    T* dst = (T*)a.keep + ((int64_t)c * a.B * a.H + bh0) * 3 * md;
+    k_lact_keep<T><<<ew, 256, 0, s>>>(W1s, W3s, W2s, dst, md);
+    return hipGetLastError();
+  };
+  if ((e = keep_slot(0)) != hipSuccess) return e;
   if (n == 0) return hipSuccess;
 
   const int kslice = (int)(cdiv(cdiv(C, kSplit), 64) * 64);
@@ -708,6 +729,7 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
       sr.nq = sr.nk = C;
     }
     if (sr.nk > 0 && a.update_mask != nullptr && a.update_mask[sr.kc] == 0) sr.nk = 0;   // applied only
+    if (a.keys_only) sr.nq = 0;                                   // the backward's recompute: states only
     if (sr.nq == 0 && sr.nk == 0) continue;
     const int tq1 = (int)(cdiv(sr.nq, Wide::BQ) + cdiv(sr.nk, Wide::BQ));
     if (want()) k_lact_fwd1<T><<<(unsigned)(cdiv(m, Wide::BP / 2) * tq1 * BH), Wide::NT, 0, s>>>(q, kk, W1s, W3s, Hh, A, U, BH, n,
@@ -756,6 +778,7 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
       k_lact_wnorm<T><<<dim3((unsigned)cdiv(dh > m ? dh : m, 4), (unsigned)(BH * 3)), 256, 0, s>>>(
           W1f, W3f, W2f, W1s, W3s, W2s, dh, m);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = keep_slot(sr.kc + 1)) != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -1,0 +1,594 @@
+// Backward of the LaCT SwiGLU fast-weight layer for gfx950 (review of "Test-Time
+// Training Done Right", LaCT Model Architecture §1, eq. (3)-(4), differentiated by
+// the chain rule; the squared error summed over each chunk, plain GD).
+//
+// The states W_c (the operand copies each chunk's update starts from) are first
+// recomputed by the forward kernels, keys only, and kept.  Then, from the last
+// chunk back, with g the fp32 gradient with respect to the state after chunk c
+// (zero after the last one):
+//   queries (applied with W_{c+1}, or with W_c in apply-then-update order):
+//     Aq = Q W1^T, Uq = Q W3^T, Hq = silu(Aq) Uq, dHq = dO W2,
+//     dAq = dHq Uq silu'(Aq), dUq = dHq silu(Aq),
+//     g2 += dO^T Hq, g1 += dAq^T Q, g3 += dUq^T Q, dq = dAq W1 + dUq W3;
+//   the update W_{c+1} = W_c - eta G(W_c; k, v), with upstream gG = -eta g:
+//     A = k W1^T, U = k W3^T, S = silu(A), Hh = S U, R = Hh W2^T - v,
+//     dH = R W2, dA = dH U silu'(A), dU = dH S            (the forward's gradient)
+//     ddA = k gG1^T, ddU = k gG3^T,
+//     ddH = ddA U silu'(A) + ddU S,
+//     dR = Hh gG2^T + ddH W2^T,  dv = -dR,
+//     dHh = R gG2 + dR W2,
+//     dU_f = ddA dH silu'(A) + dHh S,
+//     dA_f = ddA dH U silu''(A) + (ddU dH + dHh U) silu'(A),
+//     dk = dA gG1 + dU gG3 + dA_f W1 + dU_f W3,
+//     g2 += R^T ddH + dR^T Hh, g1 += dA_f^T k, g3 += dU_f^T k
+//   (silu'(a) = s(1 + a(1 - s)), silu''(a) = s(1 - s)(2 + a(1 - 2s)), s the
+//   logistic function).  Finally the initial weights' gradients are g summed over
+//   the batch rows of each head.
+//
+// Every contraction is one launch of a batched engine GEMM over the (batch, head)
+// rows: out[q][p] = alpha sum_k Q[q][k] P[p][k] over one or two K streams, each
+// operand K-major or MN-major (a token-major matrix read with the tokens as K).
+// Elementwise passes between them form the gate terms.  Layouts as in the
+// forward: q, k, v, dO [BH, n, dh]; per-chunk intermediates [BH, C, m] or
+// [BH, C, dh]; states and gradients [BH, 3, m dh] (W1 [m, dh], W3 [m, dh],
+// W2 [dh, m]).
+#include <type_traits>
+
+#include "gemm.hpp"
+#include "launch.hpp"
+
+namespace ttt {
+
+namespace {
+
+template <typename T> constexpr int bsz() { return (int)sizeof(T); }
+inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+// One operand of a batched GEMM: element (r, k) of batch b at base + b bs + r ld + k
+// (K-major) or base + b bs + k ld + r (MN-major); ld and bs in elements.
+struct BOp {
+  const void* base;
+  int64_t ld, bs;
+};
+
+enum { kStoreT = 0, kStoreF32 = 1, kAccF32 = 2, kAddF32ToT = 3 };
+
+struct BGemm {
+  BOp P[2], Q[2];
+  int K[2];          // contraction length of each stream (K[1] = 0: one stream)
+  int NP, NQ, batch;
+  void* out;         // out[b][q][p] at out + b so + q ldo + p
+  int64_t ldo, so;
+  const float* add;  // kAddF32ToT: out = alpha acc + add, add[b][q][p] at add + b add_so + q ldo + p
+  int64_t add_so;
+  float alpha;
+};
+
+// Up to three GEMMs of one kind in one launch (their tiles one after the
+// other), each contraction split nsplit ways along K: split s covers K steps
+// [s ks, (s + 1) ks) of every stream and writes out + b so + s split_so.
+constexpr int kMaxSet = 3;
+struct BGemmSet {
+  BGemm g[kMaxSet];
+  int n, nsplit;
+  int64_t split_so;
+};
+
+template <typename T, bool MN, int ROWS>
+using OpOf = std::conditional_t<MN, DmaOpMN<T, Wide::NW, ROWS>, DmaOp<Wide::NW, ROWS>>;
+
+template <typename T, bool MN, int ROWS>
+__device__ __forceinline__ void init_op(OpOf<T, MN, ROWS>& op, const BOp& o, int b, int r0, int nrows, int K,
+                                        int k0 = 0) {
+  const T* base = (const T*)o.base + (int64_t)b * o.bs + (MN ? (int64_t)k0 * o.ld : (int64_t)k0);
+  if constexpr (MN)
+    op.init(base + r0, min(ROWS, nrows - r0), (uint64_t)o.ld * bsz<T>(), K);
+  else
+    op.init(base + (int64_t)r0 * o.ld, nullptr, min(ROWS, nrows - r0), (uint64_t)o.ld * bsz<T>(),
+            (unsigned)((uint64_t)K * bsz<T>()));
+}
+
+// Batched GEMM on the engine's 256 x 256 tile; PMN / QMN pick the operand
+// layouts (shared by both streams), NS the number of K streams, MODE the output.
+template <typename T, bool PMN, bool QMN, int NS, int MODE>
+TTT_GEMM_KERNEL(Wide) void k_bgemm(BGemmSet set) {
+  using G = Wide;
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  constexpr int KR = 128 / bsz<T>();
+  int id = xcd_remap(blockIdx.x, gridDim.x);
+  // which GEMM of the set: tiles of g[0], then g[1], then g[2]
+  int which = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSet - 1; ++i) {
+    const BGemm& gi = set.g[i];
+    const int tiles = ((gi.NP + G::BP - 1) / G::BP) * ((gi.NQ + G::BQ - 1) / G::BQ) * gi.batch * set.nsplit;
+    if (which == i && i + 1 < set.n && id >= tiles) {
+      id -= tiles;
+      which = i + 1;
+    }
+  }
+  const BGemm& g = set.g[which];
+  const int TP = (g.NP + G::BP - 1) / G::BP, TQ = (g.NQ + G::BQ - 1) / G::BQ, per = TP * TQ;
+  const int bs_ = id / per;
+  const int b = bs_ / set.nsplit, sp = bs_ - b * set.nsplit;
+  int tp, tq;
+  grouped_tile(id - bs_ * per, TP, TQ, 4, tp, tq);
+  const int p0 = tp * G::BP, q0 = tq * G::BQ;
+  // this split's K range, whole K steps (every stream the same)
+  const int kmax = max(g.K[0], g.K[1]);
+  const int ks = ((kmax + set.nsplit - 1) / set.nsplit + KR - 1) / KR * KR;
+  const int k0 = sp * ks;
+  const int K0 = max(0, min(ks, g.K[0] - k0)), K1 = max(0, min(ks, g.K[1] - k0));
+  typename G::Frag acc[G::NPB][G::NQB];
+  zero_acc<G>(acc);
+  if constexpr (NS == 1) {
+    OpOf<T, PMN, G::BP> op;
+    OpOf<T, QMN, G::BQ> oq;
+    init_op<T, PMN, G::BP>(op, g.P[0], b, p0, g.NP, K0, k0);
+    init_op<T, QMN, G::BQ>(oq, g.Q[0], b, q0, g.NQ, K0, k0);
+    mainloop<T, G>(op, oq, (K0 + KR - 1) / KR, acc, smem, NoHook{});
+  } else {
+    Concat<OpOf<T, PMN, G::BP>> op;
+    Concat<OpOf<T, QMN, G::BQ>> oq;
+    init_op<T, PMN, G::BP>(op.a, g.P[0], b, p0, g.NP, K0, k0);
+    init_op<T, QMN, G::BQ>(oq.a, g.Q[0], b, q0, g.NQ, K0, k0);
+    init_op<T, PMN, G::BP>(op.b, g.P[1], b, p0, g.NP, K1, k0);
+    init_op<T, QMN, G::BQ>(oq.b, g.Q[1], b, q0, g.NQ, K1, k0);
+    const int n1 = (K0 + KR - 1) / KR, n2 = (K1 + KR - 1) / KR;
+    op.n1 = oq.n1 = n1;
+    mainloop<T, G>(op, oq, n1 + n2, acc, smem, NoHook{});
+  }
+
+  // out[q][p]: staged by rows q (p contiguous), in passes when a whole tile
+  // does not fit the stage area
+  using TO = std::conditional_t<MODE == kStoreF32 || MODE == kAccF32, float, T>;
+  constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(float) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
+  const Staged<float, G::BP> st{smem};
+  const int qn = min(G::BQ, g.NQ - q0), pn = min(G::BP, g.NP - p0);
+  TO* out = (TO*)g.out + (int64_t)b * g.so + (int64_t)sp * set.split_so;
+  const float* add = g.add != nullptr ? g.add + (int64_t)b * g.add_so : nullptr;
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+#pragma unroll
+    for (int jq = 0; jq < G::NQB; ++jq) {
+      const int qq = G::acc_q(jq) - ps * RPP;
+      if (qq < 0 || qq >= RPP) continue;
+#pragma unroll
+      for (int ib = 0; ib < G::NPB; ++ib)
+        st.put4(qq, G::acc_p(ib, 0), g.alpha * acc[ib][jq][0], g.alpha * acc[ib][jq][1], g.alpha * acc[ib][jq][2],
+                g.alpha * acc[ib][jq][3]);
+    }
+    __syncthreads();
+    const int rows = max(0, min(RPP, qn - ps * RPP));
+    constexpr int SPANS = G::BP / 4;               // 4-element spans per staged row
+    for (int idx = threadIdx.x; idx < rows * SPANS; idx += G::NT) {
+      const int r = idx / SPANS, c = (idx - r * SPANS) * 4;
+      if (c >= pn) continue;                        // NP % 4 == 0
+      const int64_t o = (int64_t)(q0 + ps * RPP + r) * g.ldo + p0 + c;
+      f32x4 v = *reinterpret_cast<const f32x4*>(smem + st.off(r, c));
+      if constexpr (MODE == kAccF32) v += load4(out + o);
+      if constexpr (MODE == kAddF32ToT) v += load4(add + o);
+      store4(out + o, v[0], v[1], v[2], v[3]);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- elementwise gate terms
+
+enum { kEwH = 0, kEwKey = 1, kEwDdh = 2, kEwF = 3, kEwQ = 4 };
+
+struct EwArgs {
+  const void *A, *U, *x1, *x2, *x3, *x4;   // inputs beside A and U (by stage)
+  void *y1, *y2, *y3;                      // outputs
+  int64_t n;                               // elements per row group (C m)
+};
+
+// Eight consecutive elements per thread of [BH, C, m] buffers (contiguous):
+//   kEwH:   y1 = Hh = silu(A) U
+//   kEwKey: x1 = dH;                 y1 = dA = dH U silu'(A), y2 = dU = dH silu(A)
+//   kEwDdh: x1 = ddA, x2 = ddU;      y1 = ddH = ddA U silu'(A) + ddU silu(A)
+//   kEwF:   x1 = dH, x2 = ddA, x3 = ddU, x4 = dHh;
+//           y1 = dA_f = ddA dH U silu''(A) + (ddU dH + dHh U) silu'(A),
+//           y2 = dU_f = ddA dH silu'(A) + dHh silu(A)
+//   kEwQ:   (A, U = Aq, Uq) x1 = dHq; y1 = Hq, y2 = dAq, y3 = dUq
+template <typename T, int STAGE>
+__global__ __launch_bounds__(256) void k_lact_ew(EwArgs a) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (e >= a.n) return;
+  const int64_t o = (int64_t)blockIdx.y * a.n + e;
+  auto ld8 = [&](const void* p, float* v) {
+    const T* t = (const T*)p + o;
+    const f32x4 x0 = load4(t), x1 = load4(t + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = x0[i];
+      v[4 + i] = x1[i];
+    }
+  };
+  auto st8 = [&](void* p, const float* v) {
+    T* t = (T*)p + o;
+    store4(t, v[0], v[1], v[2], v[3]);
+    store4(t + 4, v[4], v[5], v[6], v[7]);
+  };
+  float A[8], U[8], x1[8], x2[8], x3[8], x4[8], y1[8], y2[8], y3[8];
+  ld8(a.A, A);
+  ld8(a.U, U);
+  if constexpr (STAGE != kEwH) ld8(a.x1, x1);
+  if constexpr (STAGE == kEwDdh || STAGE == kEwF) ld8(a.x2, x2);
+  if constexpr (STAGE == kEwF) {
+    ld8(a.x3, x3);
+    ld8(a.x4, x4);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float s = sigmoid_f(A[i]);
+    const float S = A[i] * s;                             // silu(A)
+    const float s1 = s * (1.0f + A[i] * (1.0f - s));      // silu'(A)
+    if constexpr (STAGE == kEwH) {
+      y1[i] = S * U[i];
+    } else if constexpr (STAGE == kEwKey) {
+      y1[i] = x1[i] * U[i] * s1;
+      y2[i] = x1[i] * S;
+    } else if constexpr (STAGE == kEwDdh) {
+      y1[i] = x1[i] * U[i] * s1 + x2[i] * S;
+    } else if constexpr (STAGE == kEwF) {
+      const float s2 = s * (1.0f - s) * (2.0f + A[i] * (1.0f - 2.0f * s));   // silu''(A)
+      y1[i] = x2[i] * x1[i] * U[i] * s2 + (x3[i] * x1[i] + x4[i] * U[i]) * s1;
+      y2[i] = x2[i] * x1[i] * s1 + x4[i] * S;
+    } else {
+      y1[i] = S * U[i];
+      y2[i] = x1[i] * U[i] * s1;
+      y3[i] = x1[i] * S;
+    }
+  }
+  st8(a.y1, y1);
+  if constexpr (STAGE == kEwKey || STAGE == kEwF || STAGE == kEwQ) st8(a.y2, y2);
+  if constexpr (STAGE == kEwQ) st8(a.y3, y3);
+}
+
+// dst[bh][t][j] = -src[bh][t][j] for one chunk: src [BH, C, dh] contiguous, dst
+// rows of [BH, n, dh] at the chunk's offset (dst already offset; row group stride
+// dstride); four elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lact_neg(const T* __restrict__ src, T* __restrict__ dst, int64_t n,
+                                                  int64_t dstride) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  const f32x4 x = load4(src + (int64_t)blockIdx.y * n + e);
+  store4(dst + (int64_t)blockIdx.y * dstride + e, -x[0], -x[1], -x[2], -x[3]);
+}
+
+// R = Y - v for one chunk, formed in fp32 and rounded once: Y [BH, C, dh] fp32,
+// v rows of [BH, n, dh] at the chunk's offset (row group stride vstride), R
+// [BH, C, dh]; four elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lact_residual(const float* __restrict__ Y, const T* __restrict__ v,
+                                                       T* __restrict__ R, int64_t n, int64_t vstride) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  const f32x4 x = load4(Y + (int64_t)blockIdx.y * n + e) - load4(v + (int64_t)blockIdx.y * vstride + e);
+  store4(R + (int64_t)blockIdx.y * n + e, x[0], x[1], x[2], x[3]);
+}
+
+// gG = scale * g over the [BH, 3, m dh] gradients (operand dtype), four per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lact_gscale(const float* __restrict__ g, T* __restrict__ out, int64_t n,
+                                                     float scale) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  const f32x4 x = load4(g + e) * scale;
+  store4(out + e, x[0], x[1], x[2], x[3]);
+}
+
+// g += sum over the nsplit partials part[s] (fp32, n elements each, splits in
+// order), four elements per thread.
+__global__ __launch_bounds__(256) void k_lact_gacc(const float* __restrict__ part, float* __restrict__ g, int64_t n,
+                                                   int nsplit) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  f32x4 x = load4(g + e);
+  for (int sp = 0; sp < nsplit; ++sp) x += load4(part + (int64_t)sp * n + e);
+  store4(g + e, x[0], x[1], x[2], x[3]);
+}
+
+// out[h][e] = sum over the B rows of g[b H + h][w][e] (rows in order): the
+// initial weights' gradients of head h; grid.y = h * 3 + w.
+__global__ __launch_bounds__(256) void k_lact_gsum(const float* __restrict__ g, float* __restrict__ d1,
+                                                   float* __restrict__ d3, float* __restrict__ d2, int B, int H,
+                                                   int64_t md) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= md) return;
+  const int h = blockIdx.y / 3, w = blockIdx.y % 3;
+  f32x4 s = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < B; ++b) s += load4(g + (((int64_t)b * H + h) * 3 + w) * md + e);
+  float* out = (w == 0 ? d1 : (w == 1 ? d3 : d2)) + (int64_t)h * md + e;
+  store4(out, s[0], s[1], s[2], s[3]);
+}
+
+// ---------------------------------------------------------------- host side
+
+// Workspace of the backward: the forward's own (for the recompute), the kept
+// states, the fp32 state gradient and its scaled operand copy, the per-chunk
+// intermediates and one fp32 [BH, C, dh] partial.
+// The state gradient's contractions over a chunk's tokens are split this many
+// ways (with 4 x 512 x 1024 states, three gradients of 32 tiles each would
+// leave most of the GPU idle); the splits' fp32 partials are then added in order.
+constexpr int kGradSplit = 4;
+
+struct LactBwdWs {
+  size_t fwd, keep, g, gG, cm[18], cd[2], part, gpart, total;
+};
+
+template <typename T>
+LactBwdWs lact_bwd_layout(int B, int H, int n, int dh, int m, int C) {
+  LactBwdWs w{};
+  const size_t e = sizeof(T), BH = (size_t)B * H, md = (size_t)m * dh, k = (size_t)(C > 0 ? n / C : 0);
+  size_t o = 0;
+  w.fwd = o;
+  o += al256(lact_workspace_bytes<T>(B, H, n, dh, m, C));
+  w.keep = o;
+  o += al256((k + 1) * BH * 3 * md * e);
+  w.g = o;
+  o += al256(BH * 3 * md * 4);
+  w.gG = o;
+  o += al256(BH * 3 * md * e);
+  for (int i = 0; i < 18; ++i) {
+    w.cm[i] = o;
+    o += al256(BH * (size_t)C * m * e);
+  }
+  for (int i = 0; i < 2; ++i) {
+    w.cd[i] = o;
+    o += al256(BH * (size_t)C * dh * e);
+  }
+  w.part = o;
+  o += al256(BH * (size_t)C * dh * 4);
+  w.gpart = o;
+  o += al256((size_t)kGradSplit * BH * 3 * md * 4);
+  w.total = o;
+  return w;
+}
+
+template <typename T, bool PMN, bool QMN, int NS, int MODE>
+hipError_t bgemm_set(const BGemmSet& set, hipStream_t s) {
+  int64_t tiles = 0;
+  for (int i = 0; i < set.n; ++i)
+    tiles += cdiv64(set.g[i].NP, Wide::BP) * cdiv64(set.g[i].NQ, Wide::BQ) * set.g[i].batch * set.nsplit;
+  if (tiles == 0) return hipSuccess;
+  k_bgemm<T, PMN, QMN, NS, MODE><<<(unsigned)tiles, Wide::NT, 0, s>>>(set);
+  return hipGetLastError();
+}
+
+template <typename T, bool PMN, bool QMN, int NS, int MODE>
+hipError_t bgemm(const BGemm& g, hipStream_t s) {
+  if (g.NP <= 0 || g.NQ <= 0 || g.batch <= 0) return hipSuccess;
+  BGemmSet set{};
+  set.g[0] = g;
+  set.n = 1;
+  set.nsplit = 1;
+  return bgemm_set<T, PMN, QMN, NS, MODE>(set, s);
+}
+
+template <typename T, int STAGE>
+hipError_t ew(const EwArgs& a, int BH, hipStream_t s) {
+  k_lact_ew<T, STAGE><<<dim3((unsigned)cdiv64(a.n / 8, 256), (unsigned)BH), 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+template <typename T>
+size_t lact_bwd_workspace_bytes(int B, int H, int n, int dh, int m, int C) {
+  return lact_bwd_layout<T>(B, H, n, dh, m, C).total;
+}
+
+template <typename T>
+hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
+  const int B = a.B, H = a.H, n = a.n, dh = a.dh, m = a.m, C = a.C;
+  const int BH = B * H;
+  const int64_t md = (int64_t)m * dh;
+  hipError_t e;
+  if (BH == 0) return hipSuccess;
+  const LactBwdWs L = lact_bwd_layout<T>(B, H, n, dh, m, C);
+  float* g = (float*)(a.ws + L.g);
+  T* gG = (T*)(a.ws + L.gG);
+  if ((e = launch_zero<float>(g, (int64_t)BH * 3 * md, s)) != hipSuccess) return e;
+  if (n > 0) {
+    // the states: the forward's kernels on the keys alone, every chunk's state kept
+    LactArgs f{};
+    f.B = B;
+    f.H = H;
+    f.n = n;
+    f.dh = dh;
+    f.m = m;
+    f.C = C;
+    f.order = a.order;
+    f.eta = a.eta;
+    f.q = a.q;
+    f.k = a.k;
+    f.v = a.v;
+    f.W1 = a.W1;
+    f.W3 = a.W3;
+    f.W2 = a.W2;
+    f.O = nullptr;
+    // the recompute's own final states land in the gradient buffer, cleared after it
+    f.W1f = g;
+    f.W3f = g + (int64_t)BH * md;
+    f.W2f = g + 2 * (int64_t)BH * md;
+    f.ws = a.ws + L.fwd;
+    f.keys_only = 1;
+    f.keep = a.ws + L.keep;
+    if ((e = launch_lact<T>(f, s)) != hipSuccess) return e;
+    if ((e = launch_zero<float>(g, (int64_t)BH * 3 * md, s)) != hipSuccess) return e;
+  }
+  const int k = C > 0 ? n / C : 0;
+  const T* keep = (const T*)(a.ws + L.keep);
+  T* cm[18];
+  for (int i = 0; i < 18; ++i) cm[i] = (T*)(a.ws + L.cm[i]);
+  T* A = cm[0];
+  T* U = cm[1];
+  T* Hh = cm[2];
+  T* dH = cm[3];
+  T* dA = cm[4];
+  T* dU = cm[5];
+  T* ddA = cm[6];
+  T* ddU = cm[7];
+  T* ddH = cm[8];
+  T* dHh = cm[9];
+  T* dAf = cm[10];
+  T* dUf = cm[11];
+  T* Aq = cm[12];
+  T* Uq = cm[13];
+  T* Hq = cm[14];
+  T* dHq = cm[15];
+  T* dAq = cm[16];
+  T* dUq = cm[17];
+  T* R = (T*)(a.ws + L.cd[0]);
+  T* dR = (T*)(a.ws + L.cd[1]);
+  float* part = (float*)(a.ws + L.part);
+  float* gpart = (float*)(a.ws + L.gpart);
+  // the three state-gradient contractions of a phase, split over the tokens, then added into g
+  auto grad_set = [&](auto launch, BGemm g2, BGemm g1, BGemm g3) -> hipError_t {
+    BGemmSet set{};
+    set.g[0] = g2;
+    set.g[1] = g1;
+    set.g[2] = g3;
+    set.n = 3;
+    set.nsplit = kGradSplit;
+    set.split_so = (int64_t)BH * 3 * md;
+    hipError_t r = launch(set);
+    if (r != hipSuccess) return r;
+    const int64_t n = (int64_t)BH * 3 * md;
+    k_lact_gacc<<<(unsigned)cdiv64(n / 4, 256), 256, 0, s>>>(gpart, g, n, kGradSplit);
+    return hipGetLastError();
+  };
+  const int64_t S3 = 3 * md;                                 // row-group stride of states and gradients
+  const int64_t Sn = (int64_t)n * dh, Scm = (int64_t)C * m, Scd = (int64_t)C * dh;
+  // a [BH, C, x] intermediate as a K-major (token rows) or MN-major (tokens as K) operand
+  auto cmK = [&](const T* p) { return BOp{p, m, Scm}; };
+  auto cdK = [&](const T* p) { return BOp{p, dh, Scd}; };
+  auto one = [&](BOp P, BOp Q, int K, int NP, int NQ, void* out, int64_t ldo, int64_t so, float alpha = 1.0f,
+                 const float* add = nullptr) {
+    BGemm gm{};
+    gm.P[0] = P;
+    gm.Q[0] = Q;
+    gm.K[0] = K;
+    gm.NP = NP;
+    gm.NQ = NQ;
+    gm.batch = BH;
+    gm.out = out;
+    gm.ldo = ldo;
+    gm.so = so;
+    gm.alpha = alpha;
+    gm.add = add;
+    return gm;
+  };
+  auto two = [&](BGemm gm, BOp P2, BOp Q2, int K2) {
+    gm.P[1] = P2;
+    gm.Q[1] = Q2;
+    gm.K[1] = K2;
+    return gm;
+  };
+
+  // queries of a chunk applied with the state W (slot pointer, rows 3 m dh apart)
+  auto query_backward = [&](const T* W, int c) -> hipError_t {
+    const T *W1 = W, *W3 = W + md, *W2 = W + 2 * md;
+    const BOp Qc{(const T*)a.q + (int64_t)c * C * dh, dh, Sn};
+    const BOp dOc{(const T*)a.dO + (int64_t)c * C * dh, dh, Sn};
+    hipError_t r;
+    if ((r = bgemm<T, false, false, 1, kStoreT>(one({W1, dh, S3}, Qc, dh, m, C, Aq, m, Scm), s)) != hipSuccess) return r;
+    if ((r = bgemm<T, false, false, 1, kStoreT>(one({W3, dh, S3}, Qc, dh, m, C, Uq, m, Scm), s)) != hipSuccess) return r;
+    if ((r = bgemm<T, true, false, 1, kStoreT>(one({W2, m, S3}, dOc, dh, m, C, dHq, m, Scm), s)) != hipSuccess) return r;
+    EwArgs ea{Aq, Uq, dHq, nullptr, nullptr, nullptr, Hq, dAq, dUq, Scm};
+    if ((r = ew<T, kEwQ>(ea, BH, s)) != hipSuccess) return r;
+    // g2 += dO^T Hq, g1 += dAq^T Q, g3 += dUq^T Q
+    r = grad_set([&](const BGemmSet& set) { return bgemm_set<T, true, true, 1, kStoreF32>(set, s); },
+                 one(cmK(Hq), dOc, C, m, dh, gpart + 2 * md, m, S3), one(Qc, cmK(dAq), C, dh, m, gpart, dh, S3),
+                 one(Qc, cmK(dUq), C, dh, m, gpart + md, dh, S3));
+    if (r != hipSuccess) return r;
+    // dq = dAq W1 + dUq W3
+    return bgemm<T, true, false, 2, kStoreT>(
+        two(one({W1, dh, S3}, cmK(dAq), m, dh, C, (T*)a.dq + (int64_t)c * C * dh, dh, Sn), {W3, dh, S3}, cmK(dUq), m),
+        s);
+  };
+
+  // the update of chunk c from the state W, upstream gG = -eta g
+  auto update_backward = [&](const T* W, int c) -> hipError_t {
+    const T *W1 = W, *W3 = W + md, *W2 = W + 2 * md;
+    const T *gG1 = gG, *gG3 = gG + md, *gG2 = gG + 2 * md;
+    const BOp Kc{(const T*)a.k + (int64_t)c * C * dh, dh, Sn};
+    hipError_t r;
+    k_lact_gscale<T><<<(unsigned)cdiv64((int64_t)BH * S3 / 4, 256), 256, 0, s>>>(g, gG, (int64_t)BH * S3, -a.eta);
+    if ((r = hipGetLastError()) != hipSuccess) return r;
+    // the forward's key pass at W
+    if ((r = bgemm<T, false, false, 1, kStoreT>(one({W1, dh, S3}, Kc, dh, m, C, A, m, Scm), s)) != hipSuccess) return r;
+    if ((r = bgemm<T, false, false, 1, kStoreT>(one({W3, dh, S3}, Kc, dh, m, C, U, m, Scm), s)) != hipSuccess) return r;
+    EwArgs eh{A, U, nullptr, nullptr, nullptr, nullptr, Hh, nullptr, nullptr, Scm};
+    if ((r = ew<T, kEwH>(eh, BH, s)) != hipSuccess) return r;
+    // R = Hh W2^T - v: Y into the fp32 partial, then the residual formed in fp32 as one rounding
+    if ((r = bgemm<T, false, false, 1, kStoreF32>(one({W2, m, S3}, cmK(Hh), m, dh, C, part, dh, Scd), s)) != hipSuccess)
+      return r;
+    k_lact_residual<T><<<dim3((unsigned)cdiv64(Scd / 4, 256), (unsigned)BH), 256, 0, s>>>(
+        part, (const T*)a.v + (int64_t)c * C * dh, R, Scd, Sn);
+    if ((r = hipGetLastError()) != hipSuccess) return r;
+    if ((r = bgemm<T, true, false, 1, kStoreT>(one({W2, m, S3}, cdK(R), dh, m, C, dH, m, Scm), s)) != hipSuccess) return r;
+    EwArgs ek{A, U, dH, nullptr, nullptr, nullptr, dA, dU, nullptr, Scm};
+    if ((r = ew<T, kEwKey>(ek, BH, s)) != hipSuccess) return r;
+    // through G1 = dA^T k, G3 = dU^T k
+    if ((r = bgemm<T, false, false, 1, kStoreT>(one({gG1, dh, S3}, Kc, dh, m, C, ddA, m, Scm), s)) != hipSuccess) return r;
+    if ((r = bgemm<T, false, false, 1, kStoreT>(one({gG3, dh, S3}, Kc, dh, m, C, ddU, m, Scm), s)) != hipSuccess) return r;
+    EwArgs ed{A, U, ddA, ddU, nullptr, nullptr, ddH, nullptr, nullptr, Scm};
+    if ((r = ew<T, kEwDdh>(ed, BH, s)) != hipSuccess) return r;
+    // dR = Hh gG2^T + ddH W2^T; dv = -dR
+    if ((r = bgemm<T, false, false, 2, kStoreT>(
+             two(one({gG2, m, S3}, cmK(Hh), m, dh, C, dR, dh, Scd), {W2, m, S3}, cmK(ddH), m), s)) != hipSuccess)
+      return r;
+    k_lact_neg<T><<<dim3((unsigned)cdiv64(Scd / 4, 256), (unsigned)BH), 256, 0, s>>>(
+        dR, (T*)a.dv + (int64_t)c * C * dh, Scd, Sn);
+    if ((r = hipGetLastError()) != hipSuccess) return r;
+    // dHh = R gG2 + dR W2
+    if ((r = bgemm<T, true, false, 2, kStoreT>(
+             two(one({gG2, m, S3}, cdK(R), dh, m, C, dHh, m, Scm), {W2, m, S3}, cdK(dR), dh), s)) != hipSuccess)
+      return r;
+    EwArgs ef{A, U, dH, ddA, ddU, dHh, dAf, dUf, nullptr, Scm};
+    if ((r = ew<T, kEwF>(ef, BH, s)) != hipSuccess) return r;
+    // dk = (dA gG1 + dU gG3) + (dA_f W1 + dU_f W3), the first pair in fp32
+    if ((r = bgemm<T, true, false, 2, kStoreF32>(
+             two(one({gG1, dh, S3}, cmK(dA), m, dh, C, part, dh, Scd), {gG3, dh, S3}, cmK(dU), m), s)) != hipSuccess)
+      return r;
+    {
+      // the second pair, written as the chunk's rows of dk (row group stride n dh) with the first pair added
+      BGemm gk = two(one({W1, dh, S3}, cmK(dAf), m, dh, C, (T*)a.dk + (int64_t)c * C * dh, dh, Sn),
+                     {W3, dh, S3}, cmK(dUf), m);
+      gk.add = part;
+      gk.add_so = Scd;
+      if ((r = bgemm<T, true, false, 2, kAddF32ToT>(gk, s)) != hipSuccess) return r;
+    }
+    // g2 += R^T ddH + dR^T Hh, g1 += dA_f^T k, g3 += dU_f^T k (the last two as one-stream members of a
+    // two-stream set: their second stream is empty)
+    BGemm g1 = one(Kc, cmK(dAf), C, dh, m, gpart, dh, S3), g3 = one(Kc, cmK(dUf), C, dh, m, gpart + md, dh, S3);
+    g1 = two(g1, g1.P[0], g1.Q[0], 0);
+    g3 = two(g3, g3.P[0], g3.Q[0], 0);
+    return grad_set([&](const BGemmSet& set) { return bgemm_set<T, true, true, 2, kStoreF32>(set, s); },
+                    two(one(cmK(ddH), cdK(R), C, m, dh, gpart + 2 * md, m, S3), cmK(Hh), cdK(dR), C), g1, g3);
+  };
+
+  const int64_t slot = (int64_t)BH * S3;
+  for (int c = k - 1; c >= 0; --c) {
+    const T* Wc = keep + (int64_t)c * slot;
+    const T* Wn = keep + (int64_t)(c + 1) * slot;
+    if (a.order == 0 && (e = query_backward(Wn, c)) != hipSuccess) return e;
+    if ((e = update_backward(Wc, c)) != hipSuccess) return e;
+    if (a.order != 0 && (e = query_backward(Wc, c)) != hipSuccess) return e;
+  }
+  k_lact_gsum<<<dim3((unsigned)cdiv64(md / 4, 256), (unsigned)(3 * H)), 256, 0, s>>>(g, a.dW1, a.dW3, a.dW2, B, H, md);
+  return hipGetLastError();
+}
+
+template size_t lact_bwd_workspace_bytes<float>(int, int, int, int, int, int);
+template size_t lact_bwd_workspace_bytes<bf16>(int, int, int, int, int, int);
+template hipError_t launch_lact_backward<float>(const LactBwdArgs&, hipStream_t);
+template hipError_t launch_lact_backward<bf16>(const LactBwdArgs&, hipStream_t);
+
+}  // namespace ttt

@@ -147,7 +147,25 @@ struct LactArgs {
   int muon;                           // 1: step along Muon(g) (Newton-Schulz) instead of g
   hipStream_t side;                   // caller's side stream for the second row group, or null: one chain
   hipEvent_t fork, join;              // caller's events ordering the side stream's work within the call
+  // backward's recompute: keys only (no query is applied, O is not written), and every state kept:
+  // keep [k + 1, B H, 3, m dh] dtype, slot c = the operand copies (W1, W3, W2) before chunk c's update
+  int keys_only;
+  void* keep;
 };
+template <typename T>
+size_t lact_bwd_workspace_bytes(int B, int H, int n, int dh, int m, int C);
+// Backward of the LaCT layer (squared error, plain GD, no other variant): dq, dk, dv [B, H, n, dh] dtype and the
+// initial weights' gradients dW1, dW3 [H, m, dh], dW2 [H, dh, m] fp32, given dO; every state recomputed first.
+struct LactBwdArgs {
+  int B, H, n, dh, m, C, order;
+  float eta;
+  const void *q, *k, *v, *W1, *W3, *W2, *dO;
+  void *dq, *dk, *dv;
+  float *dW1, *dW3, *dW2;
+  char* ws;
+};
+template <typename T>
+hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s);
 template <typename T>
 size_t lact_workspace_bytes(int B, int H, int n, int dh, int m, int C);
 template <typename T>

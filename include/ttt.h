@@ -527,6 +527,37 @@ int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta,
                        void* O, float* W1_f, float* W3_f, float* W2_f,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes for ttt_lact_swiglu_backward: the forward's own
+ * (ttt_lact_workspace_bytes), every chunk's state ((n / chunk + 1) B H 3 m dh
+ * dtype), the state gradient (3 B H m dh fp32 and a dtype copy) and the
+ * per-chunk intermediates (18 B H chunk m and 2 B H chunk dh dtype, B H chunk
+ * dh fp32). */
+int ttt_lact_backward_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* bytes);
+
+/* Gradients of a loss that depends on the output O of ttt_lact_swiglu (the
+ * squared error, plain GD; no mask, per-token rates, dot loss, normalisation or
+ * Muon) with respect to every input, given dO = dLoss/dO [B, H, n, dh] (dtype)
+ * (review of "Test-Time Training Done Right", LaCT Model Architecture §1,
+ * eq. (3)-(4), by the chain rule through the chunk loop):
+ *   dq, dk, dv   [B, H, n, dh] dtype
+ *   dW1, dW3     [H, m, dh] fp32    gradients of the initial weights, summed
+ *   dW2          [H, dh, m] fp32    over the batch rows (they share them)
+ * Each update W' = W - eta G(W; k, v) is differentiated through G itself, so
+ * the second derivatives of the SwiGLU loss enter (through silu'' among
+ * others).  The call first recomputes every chunk's state with the forward
+ * kernels (keys only) and keeps them in the workspace, then runs the chunks
+ * from the last back: the query apply's backward with the state it saw (after
+ * the chunk's update, or before it in TTT_APPLY_THEN_UPDATE order) and the
+ * update's backward, each a few batched engine GEMMs over the (batch, head)
+ * rows and elementwise passes.  dtype, sizes and errors as for
+ * ttt_lact_swiglu; batch == 0 gives zero weight gradients, seq_len == 0 zero
+ * weight gradients and nothing else. */
+int ttt_lact_swiglu_backward(const ttt_lact_shape* shape, int dtype, int order, float eta,
+                             const void* q, const void* k, const void* v,
+                             const void* W1, const void* W3, const void* W2, const void* dO,
+                             void* dq, void* dk, void* dv, float* dW1, float* dW3, float* dW2,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

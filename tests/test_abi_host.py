@@ -357,6 +357,30 @@ def test_lact_validation():
                                       *args[6:], _fake(), out.value, None) == cw.TTT_ERR_ARG
 
 
+def test_lact_backward_validation():
+    lib = cw.lib()
+    out = ctypes.c_size_t(0)
+    good = cw.LactShape(1, 4, 8192, 512, 1024, 4096)
+    assert lib.ttt_lact_backward_workspace_bytes(ctypes.byref(good), cw.TTT_BF16, ctypes.byref(out)) == cw.TTT_OK
+    fwd = ctypes.c_size_t(0)
+    assert lib.ttt_lact_workspace_bytes(ctypes.byref(good), cw.TTT_BF16, ctypes.byref(fwd)) == cw.TTT_OK
+    # the forward's workspace, three kept states of 3 m dh per row, and the gradients and intermediates beside
+    assert out.value > fwd.value + 3 * 4 * 3 * 512 * 1024 * 2
+    bad = cw.LactShape(1, 4, 8000, 512, 1024, 4096)
+    assert lib.ttt_lact_backward_workspace_bytes(ctypes.byref(bad), cw.TTT_BF16, ctypes.byref(out)) == \
+        cw.TTT_ERR_SHAPE
+    args = [_fake() for _ in range(13)]
+    nb = ctypes.c_size_t(0)
+    lib.ttt_lact_backward_workspace_bytes(ctypes.byref(good), cw.TTT_BF16, ctypes.byref(nb))
+    call = lambda order, eta, a, ws, nbytes: lib.ttt_lact_swiglu_backward(ctypes.byref(good), cw.TTT_BF16, order, eta,
+                                                                          *a, ws, nbytes, None)
+    assert call(5, 1.0, args, _fake(), nb.value) == cw.TTT_ERR_ARG                 # unknown order
+    assert call(0, float("inf"), args, _fake(), nb.value) == cw.TTT_ERR_ARG        # non-finite eta
+    assert call(0, 1.0, [None] + args[1:], _fake(), nb.value) == cw.TTT_ERR_ARG   # null q
+    assert call(0, 1.0, args, _fake(), nb.value - 1) == cw.TTT_ERR_WORKSPACE
+    assert call(0, 1.0, args, None, nb.value) == cw.TTT_ERR_WORKSPACE
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     H = torch.zeros(1, 16, 8)

@@ -2,7 +2,7 @@
 
 The library enqueues kernels only -- no allocation, copy or memset -- and the LaCT call given a side stream adds
 an event fork and join with it, which a capture records as parallel branches.  The backward entry points (the dot and MSE
-chunk loops, the whole dot layer) are captured the same way.  Each graph is replayed three times with
+chunk loops, the whole dot layer, the LaCT layer) are captured the same way.  Each graph is replayed three times with
 the outputs clobbered, eager calls and synchronisations in between, and every replay must reproduce the eager
 call's bits.
 """
@@ -32,6 +32,14 @@ def _lact(two_chains):
     return lambda: cw.ttt_lact_swiglu(*args, side=side)
 
 
+def _lact_backward():
+    cfg = ti.LactConfig("graph", 2, 2, 384, 64, 128, 128, 0.7, "update_then_apply", "bf16", seed=23)
+    g = {k: v.cuda() for k, v in ti.lact_inputs(cfg).items()}
+    dO = torch.randn(*g["q"].shape, generator=torch.Generator().manual_seed(24)).to(g["q"].dtype).cuda()
+    return lambda: cw.ttt_lact_swiglu_backward(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], dO, cfg.chunk,
+                                               cfg.eta, cfg.order)
+
+
 def _backward(kind):
     cfg = ti.InplaceConfig("graph", 2, 512, 264, 392, 128, 0.05 if kind != "mse_backward" else 0.5,
                            "mse" if kind == "mse_backward" else "dot", "bf16", seed=19, backward=True)
@@ -44,10 +52,11 @@ def _backward(kind):
     return lambda: fn(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta)
 
 
-@pytest.mark.parametrize("kind", ["dot", "mse", "lact", "lact_side", "backward", "mse_backward", "layer_backward"])
+@pytest.mark.parametrize("kind", ["dot", "mse", "lact", "lact_side", "backward", "mse_backward", "layer_backward",
+                                  "lact_backward"])
 def test_graph_replays_match_eager(kind):
-    call = (_lact(kind == "lact_side") if kind.startswith("lact") else _backward(kind) if "backward" in kind
-            else _inplace(kind))
+    call = (_lact_backward() if kind == "lact_backward" else _lact(kind == "lact_side") if kind.startswith("lact")
+            else _backward(kind) if "backward" in kind else _inplace(kind))
     eager = call()
     torch.cuda.synchronize()
     # warm-up on a side stream, as torch asks before a capture

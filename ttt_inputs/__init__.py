@@ -134,6 +134,7 @@ class LactConfig:
     weight_norm: bool = False     # L2-normalise the weight rows after every update
     token_rates: bool = False     # draw per-token learning rates eta_tok ~ U(0, 1) (fp32)
     muon: bool = False            # the Muon update rule (Newton-Schulz orthogonalised gradients)
+    backward: bool = False        # the layer's backward (inputs of the layer and dO)
 
     @property
     def tokens(self) -> int:
@@ -152,7 +153,13 @@ class LactConfig:
     def flops(self) -> float:
         """Algorithmic flops: per token per head, key forward 6*dh*m and
         backward 8*dh*m (dH, G1, G2, G3) on the chunks that update, query apply
-        6*dh*m on every chunk."""
+        6*dh*m on every chunk.  The layer's backward executes 66*dh*m per token
+        and head: the states recomputed on the keys (14), the query apply's
+        backward with its recompute (16: Aq, Uq, dHq, the three weight
+        gradients, dq) and the update's (36: A, U, Y, dH again, ddA, ddU, dR,
+        dHh, dk's four products, the three weight gradients)."""
+        if self.backward:
+            return float(self.tokens) * self.heads * 66.0 * self.head_dim * self.hidden
         mask = self.update_mask()
         upd = 1.0 if mask is None else sum(mask) / len(mask)
         key = 14.0 - (2.0 if self.loss == "dot" else 0.0)     # the dot loss needs no key output f(k)
@@ -212,6 +219,9 @@ WORKLOADS = {
     # the same with the Muon update rule (L2-Normalize(W - Muon(g)))
     "lact_bf16_256k_muon": LactConfig("lact_bf16_256k_muon", 1, 4, 262144, 512, 1024, 4096, 0.05, seed=1004,
                                       loss="dot", weight_norm=True, token_rates=True, muon=True),
+    # the layer's backward (every input's gradient from dLoss/dO), squared error and plain GD
+    "lact_bwd_bf16_256k": LactConfig("lact_bwd_bf16_256k", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
+                                     backward=True),
     # the same with the update on every other chunk only (a strided block-wise mask)
     "lact_bf16_256k_strided": LactConfig("lact_bf16_256k_strided", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
                                          update_every=2),
