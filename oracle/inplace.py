@@ -172,7 +172,7 @@ def chunk_apply_update(Z, Vhat, W0, chunk, eta, mode):
     return O, W
 
 
-def chunk_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None):
+def chunk_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None, update_mask=None):
     """Gradients of a loss through the dot-objective chunk loop (chunk_apply_update
     with mode "dot"), given dO = dLoss/dO: returns (dZ [n, f], dVhat [n, d],
     dW0 [d, f]).  The chain rule through O_c = Z_c W_c^T (eq. (3)) and
@@ -186,10 +186,18 @@ def chunk_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None):
     documents as in inplace_layer: the state restarts from W0 at each start, so
     a delta reaches only the later states of its own document, the suffix
     sums run to the end of the document, and W0 receives every document's sum.
+    `update_mask` [n_chunks] (truthy entries update) as in inplace_layer: a
+    masked chunk's delta is not added, which is the same loop with that chunk's
+    targets zero; its targets then reach nothing, so their gradient is zero.
     The loss is taken to depend on O only (not on W_final)."""
     Z, Vhat, W0, dO = _f64(Z), _f64(Vhat), _f64(W0), _f64(dO)
     n = Z.shape[0]
     bounds = [(s, min(s + chunk, n)) for s in range(0, n, chunk)]
+    if update_mask is not None:
+        Vhat = Vhat.copy()
+        for c, (s, e) in enumerate(bounds):
+            if not update_mask[c]:
+                Vhat[s:e] = 0.0
     starts = [c == 0 or (doc_starts is not None and bool(doc_starts[c])) for c in range(len(bounds))]
     states = []                                   # W_c, the state chunk c is applied with
     W = W0.copy()
@@ -211,10 +219,14 @@ def chunk_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None):
         if starts[c]:                             # the document's first chunk: its sum reaches W0
             dW0 = dW0 + S
             S = np.zeros_like(W0)
+    if update_mask is not None:
+        for c, (s, e) in enumerate(bounds):
+            if not update_mask[c]:
+                dV[s:e] = 0.0
     return dZ, dV, dW0
 
 
-def mse_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None):
+def mse_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None, update_mask=None):
     """Gradients of a loss through the MSE chunk loop (chunk_apply_update with
     mode "mse"), given dO = dLoss/dO: returns (dZ [n, f], dVhat [n, d],
     dW0 [d, f]).  Per chunk (eq. (3)-(4)): O_c = Z_c W_c^T, R_c = Z_c W_c^T -
@@ -227,26 +239,30 @@ def mse_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None):
     and dW0 is dLoss/dW_0.  The loss is taken to depend on O only.
     `doc_starts` [n_chunks] packs documents as in inplace_layer; they are
     independent sequences, so the gradients are those of each document taken
-    alone, dW0 summed over them."""
+    alone, dW0 summed over them.  `update_mask` [n_chunks]: a masked chunk
+    takes no step (W_{c+1} = W_c), i.e. its eta/C is zero in the formulas above."""
     if doc_starts is not None:
         cuts = [c * chunk for c in range(len(doc_starts)) if c == 0 or doc_starts[c]] + [len(Z)]
-        parts = [mse_core_backward(Z[a:e], Vhat[a:e], W0, chunk, eta, dO[a:e]) for a, e in zip(cuts[:-1], cuts[1:])]
+        um = lambda a, e: None if update_mask is None else update_mask[a // chunk: (e + chunk - 1) // chunk]
+        parts = [mse_core_backward(Z[a:e], Vhat[a:e], W0, chunk, eta, dO[a:e], update_mask=um(a, e))
+                 for a, e in zip(cuts[:-1], cuts[1:])]
         return (np.concatenate([q[0] for q in parts]), np.concatenate([q[1] for q in parts]),
                 sum(q[2] for q in parts))
     Z, Vhat, W0, dO = _f64(Z), _f64(Vhat), _f64(W0), _f64(dO)
     n = Z.shape[0]
     bounds = [(s, min(s + chunk, n)) for s in range(0, n, chunk)]
+    flag = lambda c: 1.0 if update_mask is None or update_mask[c] else 0.0
     states = []
     W = W0.copy()
-    for (s, e) in bounds:                         # the forward scan, keeping the state each chunk saw
+    for c, (s, e) in enumerate(bounds):           # the forward scan, keeping the state each chunk saw
         states.append(W)
-        W = W - eta * grad_mse(W, Z[s:e], Vhat[s:e])
+        W = W - flag(c) * eta * grad_mse(W, Z[s:e], Vhat[s:e])
     dZ = np.empty_like(Z)
     dV = np.empty_like(Vhat)
     G = np.zeros_like(W0)
     for c in range(len(bounds) - 1, -1, -1):
         s, e = bounds[c]
-        Zc, Wc, a = Z[s:e], states[c], eta / (e - s)
+        Zc, Wc, a = Z[s:e], states[c], flag(c) * eta / (e - s)
         R = Zc @ Wc.T - Vhat[s:e]
         Q = Zc @ G.T
         T = dO[s:e] - a * Q
@@ -348,7 +364,8 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
     return O, W_final
 
 
-def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, dO, doc_starts=None, mode="dot"):
+def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, dO, doc_starts=None, mode="dot",
+                   update_mask=None, conv_forward=False):
     """Gradients of a loss that depends on the output O of the layer
     (inplace_layer with the causal convolution, one document per row, and the
     objective `mode`, "dot" or "mse"), given dO = dLoss/dO [B, n, d].  Returns
@@ -376,14 +393,24 @@ def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, d
     W_down0 and the convolution from zeros at each start), so the row's
     gradients are those of its documents taken one at a time: the activation
     gradients side by side, the weight gradients added.
+
+    `update_mask` [B, n_chunks] as in inplace_layer (passed to the chunk
+    loop's backward).  `conv_forward`: the forward-looking in-chunk
+    convolution (forward_chunk_conv1d), Y[t, i] = sum_j conv_w[i, j]
+    X0[t + j, i] inside t's chunk, whose gradients are
+    dconv_w[i, j] = sum_t dY[t, i] X0[t + j, i] and
+    dX0[s, i] = sum_j conv_w[i, j] dY[s - j, i], both over pairs inside one
+    chunk.
     """
     if doc_starts is not None:
         outs = []
         for b in range(len(H)):
             k = len(doc_starts[b])
             cuts = [c * chunk for c in range(k) if c == 0 or doc_starts[b][c]] + [min(k * chunk, len(H[b]))]
+            um = lambda a, e: None if update_mask is None else [update_mask[b][a // chunk: (e + chunk - 1) // chunk]]
             parts = [layer_backward(H[b:b + 1, a:e], X0[b:b + 1, a:e], W_gate, W_up, W_down0, W_target, conv_w,
-                                    chunk, eta, dO[b:b + 1, a:e], mode=mode) for a, e in zip(cuts[:-1], cuts[1:])]
+                                    chunk, eta, dO[b:b + 1, a:e], mode=mode, update_mask=um(a, e),
+                                    conv_forward=conv_forward) for a, e in zip(cuts[:-1], cuts[1:])]
             outs.append((np.concatenate([q[0] for q in parts], axis=1), np.concatenate([q[1] for q in parts], axis=1),
                          *[sum(q[i] for q in parts) for i in range(2, 7)]))
         return (np.concatenate([o[0] for o in outs]), np.concatenate([o[1] for o in outs]),
@@ -400,10 +427,11 @@ def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, d
         with np.errstate(over="ignore"):
             sg = 1.0 / (1.0 + np.exp(-A))
         Z = A * sg * U
-        Y = causal_depthwise_conv1d(X0[b], cw)
+        Y = forward_chunk_conv1d(X0[b], cw, chunk) if conv_forward else causal_depthwise_conv1d(X0[b], cw)
         V = Y @ Wt
         core = {"dot": chunk_core_backward, "mse": mse_core_backward}[mode]
-        dZ, dV, dW0_b = core(Z, V, W0, chunk, eta, dO[b])
+        dZ, dV, dW0_b = core(Z, V, W0, chunk, eta, dO[b],
+                             update_mask=None if update_mask is None else update_mask[b])
         dW0 += dW0_b
         dA = dZ * U * (sg * (1.0 + A * (1.0 - sg)))
         dU = dZ * (A * sg)
@@ -412,6 +440,13 @@ def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, d
         dH[b] = dA @ Wg + dU @ Wu
         dWt += Y.T @ dV
         dY = dV @ Wt.T
+        if conv_forward:
+            for s0 in range(0, n, chunk):
+                e0 = min(s0 + chunk, n)
+                for j in range(min(K, e0 - s0)):      # tap j reads the token j steps ahead, inside the chunk
+                    dcw[:, j] += np.sum(dY[s0: e0 - j] * X0[b, s0 + j: e0], axis=0)
+                    dX0[b, s0 + j: e0] += cw[:, j] * dY[s0: e0 - j]
+            continue
         for j in range(K):
             back = K - 1 - j              # tap j reads the token this many steps back
             if back >= n:

@@ -848,3 +848,67 @@ def test_mse_core_backward_with_documents_matches_autograd():
     np.testing.assert_allclose(dZ, tz.grad.numpy(), rtol=1e-11, atol=1e-11)
     np.testing.assert_allclose(dV, tv.grad.numpy(), rtol=1e-11, atol=1e-11)
     np.testing.assert_allclose(dW0, tw.grad.numpy(), rtol=1e-11, atol=1e-11)
+
+
+# ---------------------------------------------------------------- backward with update masks and the forward conv
+
+def _torch_loop(Z, V, W0, C, eta, mode, mask):
+    """The chunk loop (either objective) in torch float64 with an update mask: a masked chunk is applied and takes
+    no step."""
+    W = W0
+    outs = []
+    for c, s in enumerate(range(0, Z.shape[0], C)):
+        Zc, Vc = Z[s:s + C], V[s:s + C]
+        O = Zc @ W.T
+        outs.append(O)
+        if mask[c]:
+            W = W + eta * (Vc.T @ Zc) if mode == "dot" else W - (eta / Zc.shape[0]) * ((O - Vc).T @ Zc)
+    return torch.cat(outs)
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_core_backward_with_update_mask_matches_autograd(mode):
+    """A masked chunk is applied with the state it finds and leaves it unchanged: autograd of that loop gives the
+    oracle's gradients, the masked chunks' target gradient zero; an all-ones mask is the unmasked backward."""
+    rng = _rng(58)
+    n, C, d, f, eta = 15, 3, 3, 4, 0.4
+    Z, V, W0, dO = (rng.standard_normal(sh) for sh in ((n, f), (n, d), (d, f), (n, d)))
+    mask = [1, 0, 1, 0, 1]
+    back = orc.chunk_core_backward if mode == "dot" else orc.mse_core_backward
+    ours = back(Z, V, W0, C, eta, dO, update_mask=mask)
+    tz, tv, tw = (torch.tensor(a, requires_grad=True) for a in (Z, V, W0))
+    (_torch_loop(tz, tv, tw, C, eta, mode, mask) * torch.from_numpy(dO)).sum().backward()
+    for got, t in zip(ours, (tz, tv, tw)):
+        np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-11, atol=1e-12)
+    assert not ours[1][3:6].any() and not ours[1][9:12].any()
+    plain = back(Z, V, W0, C, eta, dO)
+    for a, b in zip(back(Z, V, W0, C, eta, dO, update_mask=[1] * 5), plain):
+        np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_layer_backward_forward_conv_and_mask_match_autograd(mode):
+    """The whole layer with the forward-looking in-chunk convolution (torch's grouped conv1d on each chunk, right
+    padded) and an update mask, two rows with different masks: every gradient against autograd; the forward it
+    differentiates is the oracle's layer."""
+    import torch.nn.functional as F
+    rng = _rng(59)
+    B, n, C, d, f, K, eta = 2, 12, 4, 3, 4, 3, 0.3
+    shapes = ((B, n, d), (B, n, d), (f, d), (f, d), (d, f), (d, d), (d, K))
+    args = [rng.standard_normal(sh) * 0.7 for sh in shapes]
+    dO = rng.standard_normal((B, n, d))
+    mask = np.array([[1, 0, 1], [0, 1, 1]])
+    ours = orc.layer_backward(*args, C, eta, dO, mode=mode, update_mask=mask, conv_forward=True)
+    ts = [torch.tensor(a, requires_grad=True) for a in args]
+    H, X0, Wg, Wu, W0, Wt, cw = ts
+    rows = []
+    for b in range(B):
+        Z = F.silu(H[b] @ Wg.T) * (H[b] @ Wu.T)
+        Y = torch.cat([F.conv1d(F.pad(X0[b, s:s + C].T[None], (0, K - 1)), cw[:, None, :], groups=d)[0].T
+                       for s in range(0, n, C)])
+        rows.append(_torch_loop(Z, Y @ Wt, W0, C, eta, mode, mask[b]))
+    (torch.stack(rows) * torch.from_numpy(dO)).sum().backward()
+    for got, t in zip(ours, ts):
+        np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-10, atol=1e-11)
+    O, _ = orc.inplace_layer(*args, C, eta, mode, update_mask=mask, conv_forward=True)
+    np.testing.assert_allclose(O, torch.stack(rows).detach().numpy(), rtol=1e-12, atol=1e-12)
