@@ -17,7 +17,7 @@ from ._lib import (  # noqa: F401
     TTT_ERR_UNSUPPORTED, TTT_ERR_SCRATCH_LIMIT, TTT_NOALLOC_SCRATCH_BYTES, TTT_F32, TTT_BF16, TTT_MODE_DOT,
     TTT_MODE_MSE, TTT_MODE_DOT_SCAN,
     TTT_UPDATE_THEN_APPLY, TTT_APPLY_THEN_UPDATE, TTTError, InplaceShape, LactShape, LayerOptions, LactOptions,
-    LactSideStream,
+    LactSideStream, BackwardOptions,
     lib, lib_path, exported_symbols, status_string,
     ttt_inplace_workspace_bytes, ttt_lact_workspace_bytes, ttt_vhat_workspace_bytes, ttt_update_scan_workspace_bytes,
     ttt_core_backward_workspace_bytes, ttt_core_backward, ttt_layer_backward_workspace_bytes, ttt_layer_backward,

@@ -60,6 +60,11 @@ class LactSideStream:
                 ctypes.c_void_p(self.join.cuda_event))
 
 
+class BackwardOptions(ctypes.Structure):
+    _fields_ = [("W_states", ctypes.c_void_p), ("doc_starts", ctypes.c_void_p), ("update_mask", ctypes.c_void_p),
+                ("conv_forward", ctypes.c_int)]
+
+
 class LactShape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("batch", "heads", "seq_len", "head_dim", "hidden", "chunk")]
 
@@ -92,6 +97,10 @@ _SIGNATURES = {
     "ttt_layer_backward_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
     "ttt_layer_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 18 + [_S, _P]),
     "ttt_layer_backward_mse_workspace_bytes": (_I, [ctypes.POINTER(InplaceShape), _I, _I, ctypes.POINTER(_S)]),
+    "ttt_layer_backward_ex": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F] + [_P] * 8 +
+                              [ctypes.POINTER(BackwardOptions)] + [_P] * 7 + [_P, _S, _P]),
+    "ttt_core_backward_ex": (_I, [ctypes.POINTER(InplaceShape), _I, _I, _F, _P, _P, _P, _P,
+                                  ctypes.POINTER(BackwardOptions), _P, _P, _P, _P, _S, _P]),
     "ttt_layer_backward_mse": (_I, [ctypes.POINTER(InplaceShape), _I, _F] + [_P] * 18 + [_S, _P]),
     "ttt_core_backward": (_I, [ctypes.POINTER(InplaceShape), _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S,
                                _P]),
@@ -329,11 +338,22 @@ def ttt_core_backward_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, s
     return n.value
 
 
+def _core_backward_ex(mode, shape, dt, eta, Z, Vhat, W_down0, dO, sp, dp, update_mask, dZ, dVhat, dW_down0, ws,
+                      nbytes, dev):
+    um = _flags(update_mask, "update_mask", (shape.batch, shape.seq_len // shape.chunk if shape.chunk > 0 else 0),
+                dev)
+    opts = BackwardOptions(sp, dp, ctypes.c_void_p(um.data_ptr()) if um.numel() else None, 0)
+    _check(lib().ttt_core_backward_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(Z), _ptr(Vhat),
+                                      _ptr(W_down0), _ptr(dO), ctypes.byref(opts), _ptr(dZ), _ptr(dVhat),
+                                      _ptr(dW_down0), _ptr(ws), nbytes, _stream(dev)), "ttt_core_backward_ex")
+
+
 def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVhat=None, dW_down0=None,
-                      workspace=None, W_states=None, doc_starts=None):
+                      workspace=None, W_states=None, doc_starts=None, update_mask=None):
     """Gradients through the dot chunk loop given dO = dLoss/dO [B, n, d], with the per-chunk states W_states
     [B, n // chunk, d, f] kept by the forward call, or recomputed (None); doc_starts [B, n // chunk] packs documents
-    as for the forward layer.  Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
+    and update_mask [B, n // chunk] masks updates as for the forward layer (the mask through ttt_core_backward_ex).
+    Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
     dt, dev = Z.dtype, Z.device
@@ -355,6 +375,10 @@ def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVh
     sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
     doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
     dp = ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None and doc_starts.numel() else None
+    if update_mask is not None:
+        _core_backward_ex("dot", shape, dt, eta, Z, Vhat, W_down0, dO, sp, dp, update_mask, dZ, dVhat, dW_down0, ws,
+                          nbytes, dev)
+        return dZ, dVhat, dW_down0
     _check(lib().ttt_core_backward(ctypes.byref(shape), _dt(dt), float(eta), _ptr(Z), _ptr(Vhat), _ptr(W_down0),
                                    _ptr(dO), sp, dp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
                                    _stream(dev)),
@@ -371,10 +395,10 @@ def ttt_core_backward_mse_workspace_bytes(shape: InplaceShape, dtype: torch.dtyp
 
 
 def ttt_core_backward_mse(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVhat=None, dW_down0=None,
-                          workspace=None, W_states=None, doc_starts=None):
+                          workspace=None, W_states=None, doc_starts=None, update_mask=None):
     """Gradients through the MSE chunk loop given dO = dLoss/dO [B, n, d], with the per-chunk states W_states
     [B, n // chunk, d, f] kept by the forward call, or recomputed (None); doc_starts [B, n // chunk] packs documents
-    as for the forward layer.
+    and update_mask [B, n // chunk] masks updates as for the forward layer (the mask through ttt_core_backward_ex).
     Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
@@ -397,6 +421,10 @@ def ttt_core_backward_mse(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None,
     sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
     doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
     dp = ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None and doc_starts.numel() else None
+    if update_mask is not None:
+        _core_backward_ex("mse", shape, dt, eta, Z, Vhat, W_down0, dO, sp, dp, update_mask, dZ, dVhat, dW_down0, ws,
+                          nbytes, dev)
+        return dZ, dVhat, dW_down0
     _check(lib().ttt_core_backward_mse(ctypes.byref(shape), _dt(dt), float(eta), _ptr(Z), _ptr(Vhat), _ptr(W_down0),
                                        _ptr(dO), sp, dp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
                                        _stream(dev)),
@@ -417,19 +445,20 @@ def ttt_layer_backward_mse_workspace_bytes(shape: InplaceShape, dtype: torch.dty
 
 
 def ttt_layer_backward_mse(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk: int, eta: float,
-                           W_states=None, grads=None, workspace=None, doc_starts=None):
+                           W_states=None, grads=None, workspace=None, doc_starts=None, update_mask=None,
+                           conv_forward=False):
     """ttt_layer_backward for the MSE objective (see there)."""
     return ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk, eta, W_states, grads,
-                              workspace, doc_starts, mode="mse")
+                              workspace, doc_starts, mode="mse", update_mask=update_mask, conv_forward=conv_forward)
 
 
 def ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk: int, eta: float, W_states=None,
-                       grads=None, workspace=None, doc_starts=None, mode="dot"):
+                       grads=None, workspace=None, doc_starts=None, mode="dot", update_mask=None, conv_forward=False):
     """Gradients of the layer (objective `mode`, "dot" or "mse") with respect to every input, given
     dO = dLoss/dO [B, n, d], with the per-chunk states W_states kept by the forward call or recomputed (None), and
-    doc_starts [B, n // chunk] packing documents as for the forward layer.  Returns (dH, dX0, dW_gate, dW_up,
-    dW_down0, dW_target, dconv_w): activations in the inputs' dtype, weight gradients fp32 summed over the batch
-    rows."""
+    doc_starts [B, n // chunk], update_mask [B, n // chunk] and conv_forward as the forward layer took them (the
+    last two through ttt_layer_backward_ex).  Returns (dH, dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w):
+    activations in the inputs' dtype, weight gradients fp32 summed over the batch rows."""
     if mode not in ("dot", "mse"):
         raise ValueError(f"mode must be 'dot' or 'mse', got {mode!r}")
     B, n, d = H.shape
@@ -454,6 +483,15 @@ def ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk
     sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
     doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
     dp = ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None and doc_starts.numel() else None
+    if update_mask is not None or conv_forward:
+        um = _flags(update_mask, "update_mask", (B, n // chunk if chunk > 0 else 0), dev)
+        opts = BackwardOptions(sp, dp, ctypes.c_void_p(um.data_ptr()) if um is not None and um.numel() else None,
+                               1 if conv_forward else 0)
+        _check(lib().ttt_layer_backward_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H), _ptr(X0),
+                                           _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target), _ptr(conv_w),
+                                           _ptr(dO), ctypes.byref(opts), *[_ptr(g) for g in grads], _ptr(ws),
+                                           nbytes, _stream(dev)), "ttt_layer_backward_ex")
+        return grads
     name = "ttt_layer_backward_mse" if mode == "mse" else "ttt_layer_backward"
     _check(getattr(lib(), name)(ctypes.byref(shape), _dt(dt), float(eta), _ptr(H), _ptr(X0), _ptr(W_gate),
                                 _ptr(W_up), _ptr(W_down0), _ptr(W_target), _ptr(conv_w), _ptr(dO), sp, dp,

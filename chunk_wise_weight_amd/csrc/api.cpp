@@ -266,6 +266,7 @@ struct BwdPlan {
   bool fused;
   bool saved;         // the states come from the caller
   const uint8_t* docs;  // document starts [B, k] (device) or null
+  const uint8_t* umask; // update mask [B, k] (device) or null: every chunk updates
   int S;
   size_t off_Zt, off_Vt, off_Vs, off_Zr, off_Gr, off_Wc, off_Sr, off_T, off_zero, off_Wp, off_Tot, off_dW, off_rd,
       total;
@@ -351,7 +352,10 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
   float* Tt = (float*)(ws + p.off_T);
   const T* Slast = Sr + (int64_t)(k - 1) * df;      // S_c = Sr[k - 1 - c]: stride -df from here
   int st = dev(ttt::launch_zero<T>(Z0, df, s));
-  if (st == TTT_OK && !vs_ready) st = dev(ttt::launch_scale<T>(V, Vs, (int64_t)B * n * d, eta, s));
+  // eta V^ with the targets of masked chunks zero (they add nothing to the states, so they get no gradient)
+  if (st == TTT_OK && !vs_ready) st = dev(ttt::launch_scale<T>(V, Vs, (int64_t)B * n * d, eta, s, p.umask, d, n, C));
+  if (st == TTT_OK && vs_ready && p.umask != nullptr)
+    st = dev(ttt::launch_scale<T>(Vs, Vs, (int64_t)B * n * d, 1.0f, s, p.umask, d, n, C));
   // with packed documents the suffixes restart at each document's end (the reversed order's starts), and
   // dW_down0, every document's sum, comes from a contraction over all chunks (into Sr and Tt, before the suffixes)
   const uint8_t* rd = p.docs != nullptr ? (const uint8_t*)(ws + p.off_rd) : nullptr;
@@ -373,7 +377,7 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
     T* Zr = (T*)(ws + p.off_Zr);
     T* Gr = (T*)(ws + p.off_Gr);
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zt, B, n, f, 1.0f, 0, s));
-    if (st == TTT_OK && !p.saved) st = dev(ttt::launch_transpose<T>(V, Vt, B, n, d, 1.0f, 0, s));
+    if (st == TTT_OK && !p.saved) st = dev(ttt::launch_transpose<T>(V, Vt, B, n, d, 1.0f, 0, s, p.umask, C));
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zr, B, n, f, 1.0f, C, s));
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(dO, Gr, B, n, d, 1.0f, C, s));
     if (st == TTT_OK && !p.saved) st = bwd_scan<T>(p, Zt, Vt, (const T*)W0, Wc, Tt, eta, false, ws, s, p.docs);
@@ -385,6 +389,8 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
     if (st == TTT_OK)
       st = dev(ttt::launch_apply<T>(Zt, Slast, (int64_t)k * df, -df, (T*)dV, B, n, d, f, C, eta, s));
   }
+  if (st == TTT_OK && p.umask != nullptr)      // a masked chunk's target reaches no state: its gradient is zero
+    st = dev(ttt::launch_scale<T>((const T*)dV, (T*)dV, (int64_t)B * n * d, 1.0f, s, p.umask, d, n, C));
   if (st == TTT_OK)
     st = dev(ttt::launch_dz<T>(dO, Vs, Wc, (int64_t)k * df, df, Slast, (int64_t)k * df, -df, (T*)dZ, B, n, d, f, C,
                                s));
@@ -404,6 +410,7 @@ struct MsePlan {
   int64_t B, n, d, f, C, k;
   size_t esz;
   const uint8_t* docs;  // document starts [B, k] (device) or null
+  const uint8_t* umask; // update mask [B, k] (device) or null
   size_t off_Vt, off_Gt, off_St, off_Ws, off_Wsh, off_G, off_Gsh, off_Rt, off_Tt, total;
 };
 
@@ -471,7 +478,7 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
     st = dev(ttt::launch_keep_state<T>(W0, Wcur, St, p.docs, false, B, k, c, df, s));
     if (st == TTT_OK)
       st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Ws, Wsh, nullptr, Rt, p.docs, false, B, n, d, f, C, c, eta,
-                                        s, nullptr, true));
+                                        s, p.umask, true));
   }
   // the state gradient G = dLoss/dW_{c+1}, zero after the last chunk, taken back chunk by chunk
   if (st == TTT_OK) st = dev(ttt::launch_zero<float>(G, (int64_t)B * df, s));
@@ -484,11 +491,11 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
     const T* Wc = Sb + (int64_t)c * df;                     // row b's W_c at Wc + b k d f
     // Rt = -(eta/C) R_c^T, R_c = Z_c W_c^T - V^_c
     st = dev(ttt::launch_mse_apply_gen<T>(Zt, Vt, W0, Wc, nullptr, Rt, true, B, n, d, f, C, c, -a, 0.f, 1.f, false,
-                                          s, wstride));
+                                          s, wstride, p.umask));
     // Tt = T_c^T = (dO_c - (eta/C) Z_c G^T)^T, and dV^_c = (eta/C) Z_c G^T
     if (st == TTT_OK)
       st = dev(ttt::launch_mse_apply_gen<T>(Zt, Gt, W0, Gop, (T*)dVv, Tt, true, B, n, d, f, C, c, -a, 1.0f, a, true,
-                                            s));
+                                            s, 0, p.umask));
     // dZ_c = T_c W_c - (eta/C) R_c G
     if (st == TTT_OK)
       st = dev(ttt::launch_dz_chunk<T>(Tt, Rt, Wc, wstride, Gop, df, (T*)dZv, B, n, d, f, C, c, s));
@@ -511,6 +518,7 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
 // the larger state, [2f, d] or [d, d]), and the tap-gradient partials.
 struct LayerBwdPlan {
   int mode;                     // TTT_MODE_DOT or TTT_MODE_MSE: the chunk loop differentiated
+  bool conv_fwd;                // the forward-looking in-chunk convolution for the target
   BwdPlan core;                 // its backward, dot objective
   MsePlan mcore;                // its backward, MSE objective
   int64_t B, n, d, f, C, K;
@@ -621,7 +629,7 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
   int st = dev(ttt::launch_zero<T>((T*)(ws + L.off_wzero), L.DFm, s));
   if (st == TTT_OK) st = dev(ttt::launch_produce_z<T>(H, Wg, Wu, Z, nullptr, rows, n, d, f, s));
   if (st == TTT_OK)
-    st = dev(ttt::launch_conv<T>((const T*)X0v, (const T*)cwv, Y, rows, n, d, K, docs, C, false, nullptr, s));
+    st = dev(ttt::launch_conv<T>((const T*)X0v, (const T*)cwv, Y, rows, n, d, K, docs, C, L.conv_fwd, nullptr, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Wt, WtT, 1, d, d, 1.0f, 0, s));
   if (st == TTT_OK) st = dev(ttt::launch_apply<T>(Y, WtT, 0, 0, Vs, B, n, d, d, C, mse ? 1.0f : eta, s, true));
   // the chunk loop: dZ, dV^ and dW_down0
@@ -640,7 +648,8 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
   if (st == TTT_OK) st = dev(ttt::launch_sum_rows(wWf, dWt, B, (int64_t)d * d, s));
   if (st == TTT_OK) st = dev(ttt::launch_apply<T>(dV, Wt, 0, 0, dY, B, n, d, d, C, 1.0f, s, true));
   if (st == TTT_OK)
-    st = dev(ttt::launch_conv_bwd<T>((const T*)X0v, (const T*)cwv, dY, (T*)dX0v, part, rows, n, d, K, s, docs, C));
+    st = dev(ttt::launch_conv_bwd<T>((const T*)X0v, (const T*)cwv, dY, (T*)dX0v, part, rows, n, d, K, s, docs, C,
+                                     L.conv_fwd));
   if (st == TTT_OK) st = dev(ttt::launch_sum_rows(part, dcw, (int)L.npart, (int64_t)d * K, s));
   return st;
 }
@@ -705,6 +714,10 @@ int static_scratch(hipStream_t s, char** out) {
   *out = p;
   return TTT_OK;
 }
+
+int core_backward_call(int mode, const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
+                       const void* W_down0, const void* dO, const ttt_backward_options* o, void* dZ, void* dVhat,
+                       float* dW_down0, void* workspace, size_t workspace_bytes, void* stream);
 
 }  // namespace
 
@@ -819,21 +832,9 @@ int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype,
 int ttt_core_backward(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
                       const void* W_down0, const void* dO, const void* W_states, const unsigned char* doc_starts,
                       void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes, void* stream) {
-  BwdPlan p;
-  int st = make_bwd_plan(shape, dtype, W_states != nullptr, &p, true);
-  if (st != TTT_OK) return st;
-  p.docs = doc_starts;
-  if (!finite(eta)) return TTT_ERR_ARG;
-  if (!ok_ptr(dW_down0) || (W_states != nullptr && !aligned16(W_states))) return TTT_ERR_ARG;
-  if (p.B * p.n > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(W_down0) || !ok_ptr(dO) || !ok_ptr(dZ) ||
-                        !ok_ptr(dVhat)))
-    return TTT_ERR_ARG;
-  if (p.total > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < p.total))
-    return TTT_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  if (dtype == TTT_BF16)
-    return core_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
-  return core_backward<float>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
+  const ttt_backward_options o{W_states, doc_starts, nullptr, 0};
+  return core_backward_call(TTT_MODE_DOT, shape, dtype, eta, Z, Vhat, W_down0, dO, &o, dZ, dVhat, dW_down0, workspace,
+                            workspace_bytes, stream);
 }
 
 int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states,
@@ -850,20 +851,9 @@ int ttt_core_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, 
                           const void* W_down0, const void* dO, const void* W_states, const unsigned char* doc_starts,
                           void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes,
                           void* stream) {
-  MsePlan p;
-  int st = make_mse_plan(shape, dtype, &p, W_states != nullptr);
-  if (st != TTT_OK) return st;
-  p.docs = doc_starts;
-  if (!finite(eta) || !ok_ptr(dW_down0) || (W_states != nullptr && !aligned16(W_states))) return TTT_ERR_ARG;
-  if (p.B * p.n > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(W_down0) || !ok_ptr(dO) || !ok_ptr(dZ) ||
-                        !ok_ptr(dVhat)))
-    return TTT_ERR_ARG;
-  if (p.total > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < p.total))
-    return TTT_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
-  if (dtype == TTT_BF16)
-    return mse_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
-  return mse_backward<float>(p, eta, Z, Vhat, W_down0, dO, W_states, dZ, dVhat, dW_down0, (char*)workspace, s);
+  const ttt_backward_options o{W_states, doc_starts, nullptr, 0};
+  return core_backward_call(TTT_MODE_MSE, shape, dtype, eta, Z, Vhat, W_down0, dO, &o, dZ, dVhat, dW_down0, workspace,
+                            workspace_bytes, stream);
 }
 
 int ttt_layer_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype, int saved_states, size_t* bytes) {
@@ -892,17 +882,23 @@ namespace {
 // The whole layer's backward for either objective (the entry points below).
 int layer_backward_call(int mode, const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
                         const void* W_gate, const void* W_up, const void* W_down0, const void* W_target,
-                        const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
-                        void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
-                        float* dconv_w, void* workspace, size_t workspace_bytes, void* stream) {
+                        const void* conv_w, const void* dO, const ttt_backward_options* o, void* dH, void* dX0,
+                        float* dW_gate, float* dW_up, float* dW_down0, float* dW_target, float* dconv_w,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  const ttt_backward_options none{};
+  if (o == nullptr) o = &none;
+  if (mode == TTT_MODE_DOT_SCAN) mode = TTT_MODE_DOT;
+  if ((mode != TTT_MODE_DOT && mode != TTT_MODE_MSE) || (o->conv_forward != 0 && o->conv_forward != 1))
+    return TTT_ERR_ARG;
   LayerBwdPlan p;
-  int st = make_layer_bwd_plan(shape, dtype, W_states != nullptr, &p, mode);
+  int st = make_layer_bwd_plan(shape, dtype, o->W_states != nullptr, &p, mode);
   if (st != TTT_OK) return st;
-  p.core.docs = doc_starts;
-  p.mcore.docs = doc_starts;
+  p.core.docs = p.mcore.docs = o->doc_starts;
+  p.core.umask = p.mcore.umask = o->update_mask;
+  p.conv_fwd = o->conv_forward == 1;
   if (!finite(eta)) return TTT_ERR_ARG;
   if (!ok_ptr(dW_gate) || !ok_ptr(dW_up) || !ok_ptr(dW_down0) || !ok_ptr(dW_target) || !ok_ptr(dconv_w) ||
-      (W_states != nullptr && !aligned16(W_states)))
+      (o->W_states != nullptr && !aligned16(o->W_states)))
     return TTT_ERR_ARG;
   if (p.B * p.n > 0 && (!ok_ptr(H) || !ok_ptr(X0) || !ok_ptr(W_gate) || !ok_ptr(W_up) || !ok_ptr(W_down0) ||
                         !ok_ptr(W_target) || !ok_ptr(conv_w) || !ok_ptr(dO) || !ok_ptr(dH) || !ok_ptr(dX0)))
@@ -912,10 +908,43 @@ int layer_backward_call(int mode, const ttt_inplace_shape* shape, int dtype, flo
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   if (dtype == TTT_BF16)
-    return layer_backward<bf16>(p, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, W_states, dH, dX0,
+    return layer_backward<bf16>(p, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, o->W_states, dH, dX0,
                                 dW_gate, dW_up, dW_down0, dW_target, dconv_w, ws, s);
-  return layer_backward<float>(p, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, W_states, dH, dX0,
+  return layer_backward<float>(p, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, o->W_states, dH, dX0,
                                dW_gate, dW_up, dW_down0, dW_target, dconv_w, ws, s);
+}
+
+// The chunk loop's backward for either objective (the entry points below).
+int core_backward_call(int mode, const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
+                       const void* W_down0, const void* dO, const ttt_backward_options* o, void* dZ, void* dVhat,
+                       float* dW_down0, void* workspace, size_t workspace_bytes, void* stream) {
+  const ttt_backward_options none{};
+  if (o == nullptr) o = &none;
+  if (mode == TTT_MODE_DOT_SCAN) mode = TTT_MODE_DOT;
+  if (mode != TTT_MODE_DOT && mode != TTT_MODE_MSE) return TTT_ERR_ARG;
+  const void* Ws = o->W_states;
+  size_t total;
+  BwdPlan p;
+  MsePlan q;
+  int st = mode == TTT_MODE_MSE ? make_mse_plan(shape, dtype, &q, Ws != nullptr)
+                                : make_bwd_plan(shape, dtype, Ws != nullptr, &p, true);
+  if (st != TTT_OK) return st;
+  const int64_t BN = mode == TTT_MODE_MSE ? q.B * q.n : p.B * p.n;
+  total = mode == TTT_MODE_MSE ? q.total : p.total;
+  p.docs = q.docs = o->doc_starts;
+  p.umask = q.umask = o->update_mask;
+  if (!finite(eta) || !ok_ptr(dW_down0) || (Ws != nullptr && !aligned16(Ws))) return TTT_ERR_ARG;
+  if (BN > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(W_down0) || !ok_ptr(dO) || !ok_ptr(dZ) || !ok_ptr(dVhat)))
+    return TTT_ERR_ARG;
+  if (total > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < total))
+    return TTT_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (mode == TTT_MODE_MSE)
+    return dtype == TTT_BF16 ? mse_backward<bf16>(q, eta, Z, Vhat, W_down0, dO, Ws, dZ, dVhat, dW_down0, ws, s)
+                             : mse_backward<float>(q, eta, Z, Vhat, W_down0, dO, Ws, dZ, dVhat, dW_down0, ws, s);
+  return dtype == TTT_BF16 ? core_backward<bf16>(p, eta, Z, Vhat, W_down0, dO, Ws, dZ, dVhat, dW_down0, ws, s)
+                           : core_backward<float>(p, eta, Z, Vhat, W_down0, dO, Ws, dZ, dVhat, dW_down0, ws, s);
 }
 
 }  // namespace
@@ -927,9 +956,9 @@ int ttt_layer_backward(const ttt_inplace_shape* shape, int dtype, float eta, con
                        const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
                        void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
                        float* dconv_w, void* workspace, size_t workspace_bytes, void* stream) {
-  return layer_backward_call(TTT_MODE_DOT, shape, dtype, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO,
-                             W_states, doc_starts, dH, dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w, workspace,
-                             workspace_bytes, stream);
+  const ttt_backward_options o{W_states, doc_starts, nullptr, 0};
+  return layer_backward_call(TTT_MODE_DOT, shape, dtype, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, &o,
+                             dH, dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w, workspace, workspace_bytes, stream);
 }
 
 int ttt_layer_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
@@ -937,9 +966,27 @@ int ttt_layer_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta,
                            const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
                            void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
                            float* dconv_w, void* workspace, size_t workspace_bytes, void* stream) {
-  return layer_backward_call(TTT_MODE_MSE, shape, dtype, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO,
-                             W_states, doc_starts, dH, dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w, workspace,
-                             workspace_bytes, stream);
+  const ttt_backward_options o{W_states, doc_starts, nullptr, 0};
+  return layer_backward_call(TTT_MODE_MSE, shape, dtype, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, &o,
+                             dH, dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w, workspace, workspace_bytes, stream);
+}
+
+int ttt_layer_backward_ex(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* H,
+                          const void* X0, const void* W_gate, const void* W_up, const void* W_down0,
+                          const void* W_target, const void* conv_w, const void* dO,
+                          const ttt_backward_options* options, void* dH, void* dX0, float* dW_gate, float* dW_up,
+                          float* dW_down0, float* dW_target, float* dconv_w, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return layer_backward_call(mode, shape, dtype, eta, H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, options, dH,
+                             dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w, workspace, workspace_bytes, stream);
+}
+
+int ttt_core_backward_ex(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* Z,
+                         const void* Vhat, const void* W_down0, const void* dO, const ttt_backward_options* options,
+                         void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return core_backward_call(mode, shape, dtype, eta, Z, Vhat, W_down0, dO, options, dZ, dVhat, dW_down0, workspace,
+                            workspace_bytes, stream);
 }
 
 int ttt_produce_z(const ttt_inplace_shape* shape, int dtype, const void* H, const void* W_gate, const void* W_up,

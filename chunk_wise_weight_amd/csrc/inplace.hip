@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
 // over kConvBwdGroups groups of kConvRows rows (each group inside one batch
 // row), writing its share of dconv_w to part [blocks, d, KW] (fp32), which a
 // row sum then reduces.
-template <typename T, int KW>
+template <typename T, int KW, bool FWD>
 __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ X0, const T* __restrict__ cw,
                                                   const T* __restrict__ dY, T* __restrict__ dX0,
                                                   float* __restrict__ part, int64_t rows, int n, int d,
@@ -184,13 +184,23 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ X0, cons
     const int kc = n / C_, c = pos0 / C_;
     const int lo = doc_start(docs, row, kc, c) ? c * C_ : 0;
     const int hi = c + 1 < kc && docs != nullptr && docs[row * kc + c + 1] != 0 ? (c + 1) * C_ : n;
-    // gy[i]: dY row r0 + i (zero from hi on); xs[i]: X0 row r0 - (KW-1) + i (zero before lo)
+    // causal: gy[i] = dY row r0 + i (zero from hi on), xs[i] = X0 row r0 - (KW-1) + i (zero before lo).
+    // FWD (Y[t] = sum_j w_j X0[t + j] inside t's chunk): gy[i] = dY row r0 - (KW-1) + i (zero before the
+    // chunk's first row), xs[i] = X0 row r0 + i (zero from the next chunk on); a window never leaves the chunk,
+    // so documents, which start at chunk boundaries, need nothing more.
     u32x4 gy[NIN], xs[NIN];
 #pragma unroll
     for (int i = 0; i < NIN; ++i) {
-      gy[i] = pos0 + i < hi ? *reinterpret_cast<const u32x4*>(dY + (r0 + i) * d + ch) : u32x4{0u, 0u, 0u, 0u};
-      xs[i] = pos0 + i - (KW - 1) >= lo ? *reinterpret_cast<const u32x4*>(X0 + (r0 + i - (KW - 1)) * d + ch)
+      if constexpr (FWD) {
+        gy[i] = pos0 + i - (KW - 1) >= c * C_ ? *reinterpret_cast<const u32x4*>(dY + (r0 + i - (KW - 1)) * d + ch)
+                                              : u32x4{0u, 0u, 0u, 0u};
+        xs[i] = pos0 + i < (c + 1) * C_ ? *reinterpret_cast<const u32x4*>(X0 + (r0 + i) * d + ch)
                                         : u32x4{0u, 0u, 0u, 0u};
+      } else {
+        gy[i] = pos0 + i < hi ? *reinterpret_cast<const u32x4*>(dY + (r0 + i) * d + ch) : u32x4{0u, 0u, 0u, 0u};
+        xs[i] = pos0 + i - (KW - 1) >= lo ? *reinterpret_cast<const u32x4*>(X0 + (r0 + i - (KW - 1)) * d + ch)
+                                          : u32x4{0u, 0u, 0u, 0u};
+      }
     }
 #pragma unroll
     for (int r = 0; r < RW; ++r) {
@@ -204,7 +214,7 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ X0, cons
         unpack(xs[r + j], x);
 #pragma unroll
         for (int v = 0; v < V; ++v) o[v] = fmaf(w[v][j], y[v], o[v]);
-        if (j == 0) unpack(gy[r], g);
+        if (j == 0) unpack(gy[FWD ? r + KW - 1 : r], g);       // dY row r0 + r
 #pragma unroll
         for (int v = 0; v < V; ++v) gw[v][j] = fmaf(g[v], x[v], gw[v][j]);
       }
@@ -979,12 +989,19 @@ __global__ __launch_bounds__(256) void k_doc_grad_reset(float* __restrict__ G, T
   if (any) store4(dW0 + e, a[0], a[1], a[2], a[3]);
 }
 
-// dst = scale * src over n elements, four per thread (n % 4 == 0).
+// dst = scale * src over n elements, four per thread (n % 4 == 0).  With an
+// update mask [B, k] the elements are token rows of `row` elements ([B, n, row],
+// chunks of C tokens) and the rows of masked chunks are multiplied by zero.
 template <typename T>
 __global__ __launch_bounds__(256) void k_scale(const T* __restrict__ src, T* __restrict__ dst, int64_t n,
-                                               float scale) {
+                                               float scale, const uint8_t* __restrict__ umask, int row, int ntok,
+                                               int C_) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= n) return;
+  if (umask != nullptr) {
+    const int64_t tok = e / row;                    // row % 4 == 0: the four elements share a token
+    scale *= update_flag(umask, tok / ntok, ntok / C_, (int)(tok % ntok) / C_);
+  }
   const f32x4 v = load4(src + e);
   store4(dst + e, scale * v[0], scale * v[1], scale * v[2], scale * v[3]);
 }
@@ -1026,6 +1043,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
   const int64_t row0 = (int64_t)b * n + (int64_t)c * C_ + t0;
   const uint64_t ldb = (uint64_t)f * esz<T>();
   rscale *= update_flag(umask, b, n / C_, c);       // a masked chunk's update adds zeros
+  if constexpr (GEN) oscale *= update_flag(umask, b, n / C_, c);   // (the backward: its target gets no gradient)
 
   DmaOp<G::NW, G::BP> op;
   std::conditional_t<ZNAT, DmaOp<G::NW, G::BQ>, DmaOpMN<T, G::NW, G::BQ>> oq;
@@ -1193,14 +1211,17 @@ hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int 
 
 template <typename T>
 hipError_t launch_conv_bwd(const T* X0, const T* cw, const T* dY, T* dX0, float* part, int64_t rows, int n, int d,
-                           int K, hipStream_t s, const uint8_t* docs, int C) {
+                           int K, hipStream_t s, const uint8_t* docs, int C, bool fwd) {
   if (rows == 0) return hipSuccess;
   const int64_t threads = conv_bwd_partials(rows) * (d / Vec<T>::V);
   const dim3 g((unsigned)cdiv(threads, 256));
   switch (K) {
 #define TTT_KW(KW)                                                                                            \
   case KW:                                                                                                    \
-    k_conv_bwd<T, KW><<<g, 256, 0, s>>>(X0, cw, dY, dX0, part, rows, n, d, docs, C);                          \
+    if (fwd)                                                                                                  \
+      k_conv_bwd<T, KW, true><<<g, 256, 0, s>>>(X0, cw, dY, dX0, part, rows, n, d, docs, C);                  \
+    else                                                                                                      \
+      k_conv_bwd<T, KW, false><<<g, 256, 0, s>>>(X0, cw, dY, dX0, part, rows, n, d, docs, C);                 \
     break;
     TTT_KW(1) TTT_KW(2) TTT_KW(3) TTT_KW(4) TTT_KW(5) TTT_KW(6) TTT_KW(7) TTT_KW(8)
 #undef TTT_KW
@@ -1303,9 +1324,10 @@ hipError_t launch_rev_docs(const uint8_t* docs, uint8_t* rd, int B, int k, hipSt
 }
 
 template <typename T>
-hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_t s) {
+hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_t s, const uint8_t* umask, int row,
+                        int ntok, int C) {
   if (n == 0) return hipSuccess;
-  k_scale<T><<<(unsigned)cdiv(n / 4, 256), 256, 0, s>>>(src, dst, n, scale);
+  k_scale<T><<<(unsigned)cdiv(n / 4, 256), 256, 0, s>>>(src, dst, n, scale, umask, row, ntok, C);
   return hipGetLastError();
 }
 
@@ -1331,15 +1353,15 @@ hipError_t launch_dz_chunk(const T* Tt, const T* Rt, const T* W, int64_t wsb, co
 template <typename T>
 hipError_t launch_mse_apply_gen(const T* Zt, const T* Vt, const T* W0, const T* Wcur, T* O, T* Rt, bool cont, int B,
                                 int n, int d, int f, int Cs, int c, float rscale, float vscale, float oscale, bool gen,
-                                hipStream_t s, int64_t wstride) {
+                                hipStream_t s, int64_t wstride, const uint8_t* umask) {
   const unsigned g = tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B);
   const int64_t df = (int64_t)d * f;
   if (gen)
     k_mse_apply<T, true, true><<<g, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, nullptr, n, d, f, Cs, c, rscale,
-                                                      cont, nullptr, vscale, oscale, wstride > 0 ? wstride : df);
+                                                      cont, umask, vscale, oscale, wstride > 0 ? wstride : df);
   else
     k_mse_apply<T, false, true><<<g, Wide::NT, 0, s>>>(Zt, W0, Wcur, O, Vt, Rt, nullptr, n, d, f, Cs, c, rscale,
-                                                       cont, nullptr, 0.f, 1.f, wstride > 0 ? wstride : df);
+                                                       cont, umask, 0.f, 1.f, wstride > 0 ? wstride : df);
   return hipGetLastError();
 }
 
@@ -1437,13 +1459,14 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
                                                   hipStream_t, int);                                              \
   template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int, float,   \
                                       hipStream_t, bool);                                                         \
-  template hipError_t launch_scale<T>(const T*, T*, int64_t, float, hipStream_t);                                 \
+  template hipError_t launch_scale<T>(const T*, T*, int64_t, float, hipStream_t, const uint8_t*, int, int, int);  \
   template hipError_t launch_dz<T>(const T*, const T*, const T*, int64_t, int64_t, const T*, int64_t, int64_t, T*, \
                                    int, int, int, int, int, hipStream_t, int);                                    \
   template hipError_t launch_dz_chunk<T>(const T*, const T*, const T*, int64_t, const T*, int64_t, T*, int, int,  \
                                          int, int, int, int, hipStream_t);                                        \
   template hipError_t launch_mse_apply_gen<T>(const T*, const T*, const T*, const T*, T*, T*, bool, int, int, int, \
-                                              int, int, int, float, float, float, bool, hipStream_t, int64_t);    \
+                                              int, int, int, float, float, float, bool, hipStream_t, int64_t,     \
+                                              const uint8_t*);                                                    \
   template hipError_t launch_doc_grad_reset<T>(float*, T*, float*, const uint8_t*, int, int, int, int64_t,       \
                                                hipStream_t);                                                      \
   template hipError_t launch_keep_state<T>(const T*, const T*, T*, const uint8_t*, bool, int, int, int, int64_t,  \
@@ -1453,7 +1476,7 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
   template hipError_t launch_produce_z_bwd<T>(const T*, const T*, const T*, const T*, T*, int64_t, int, int, int,  \
                                               hipStream_t);                                                       \
   template hipError_t launch_conv_bwd<T>(const T*, const T*, const T*, T*, float*, int64_t, int, int, int,        \
-                                         hipStream_t, const uint8_t*, int);                                       \
+                                         hipStream_t, const uint8_t*, int, bool);                                 \
   template hipError_t launch_zero<T>(T*, int64_t, hipStream_t);                                                   \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
                                           const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t,  \

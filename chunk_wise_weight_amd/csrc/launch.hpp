@@ -65,9 +65,11 @@ hipError_t launch_apply(const T* Zt, const T* W, int64_t wsb, int64_t wsc, T* O,
                         float oscale, hipStream_t s, bool znat = false);
 // rd [B, k]: the document starts of the reversed chunk order (see k_rev_docs).
 hipError_t launch_rev_docs(const uint8_t* docs, uint8_t* rd, int B, int k, hipStream_t s);
-// dst [n] = scale * src (n % 4 == 0).
+// dst [n] = scale * src (n % 4 == 0); with umask [B, k] the elements are [B, ntok, row] token rows of chunks of C
+// tokens, and the rows of masked chunks become zero.
 template <typename T>
-hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_t s);
+hipError_t launch_scale(const T* src, T* dst, int64_t n, float scale, hipStream_t s, const uint8_t* umask = nullptr,
+                        int row = 4, int ntok = 1, int C = 1);
 // dZ_c = dO_c W_c + V_c S_c per chunk, V = eta V^ (backward of the dot chunk
 // loop); states W_c at W + b wsb + c wsc and S_c at S + b ssb + c ssc, [d, f].
 // The rows of V and dO are ldq elements apart (0: d).
@@ -89,9 +91,10 @@ hipError_t launch_dz_chunk(const T* Tt, const T* Rt, const T* W, int64_t wsb, co
 // W_down0 at chunk 0 unless cont, else Wcur + b d f.
 // Row b's state is Wcur + b wstride (0: d f).
 template <typename T>
+// umask [B, k] (or null): a masked chunk's rscale (and, with gen, oscale) is zero.
 hipError_t launch_mse_apply_gen(const T* Zt, const T* Vt, const T* W0, const T* Wcur, T* O, T* Rt, bool cont, int B,
                                 int n, int d, int f, int C, int c, float rscale, float vscale, float oscale, bool gen,
-                                hipStream_t s, int64_t wstride = 0);
+                                hipStream_t s, int64_t wstride = 0, const uint8_t* umask = nullptr);
 // MSE backward, packed rows: where chunk c starts row b's document, dW0 += G[b] (rows in order) and G[b] (and
 // Gsh[b]) = 0.
 template <typename T>
@@ -111,11 +114,11 @@ hipError_t launch_mse_update(const T* Zt, const T* Rt, const T* W0, float* Ws, T
 template <typename T>
 hipError_t launch_produce_z_bwd(const T* H, const T* Wg, const T* Wu, const T* dZ, T* G, int64_t rows, int n, int d,
                                 int f, hipStream_t s);
-// Backward of the causal convolution: dX0 [rows, d] and the tap-gradient
-// partials part [conv_bwd_partials(rows), d, K] (fp32).
+// Backward of the causal convolution (fwd: of the forward-looking in-chunk one): dX0 [rows, d] and the
+// tap-gradient partials part [conv_bwd_partials(rows), d, K] (fp32).
 template <typename T>
 hipError_t launch_conv_bwd(const T* X0, const T* cw, const T* dY, T* dX0, float* part, int64_t rows, int n, int d,
-                           int K, hipStream_t s, const uint8_t* docs, int C);
+                           int K, hipStream_t s, const uint8_t* docs, int C, bool fwd = false);
 // Number of tap-gradient partials launch_conv_bwd writes: a thread takes
 // kConvBwdGroups groups of kConvBwdRows rows of one channel chunk.
 constexpr int kConvBwdRows = 8, kConvBwdGroups = 32;

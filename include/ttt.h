@@ -233,6 +233,29 @@ int ttt_core_apply_update_ex(const ttt_inplace_shape* shape, int dtype, int mode
                              const ttt_layer_options* options, void* O, float* W_final,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- backward passes ---- */
+
+/* Options of the backward entry points with an _ex suffix; a NULL options
+ * pointer, or all fields zero, gives the plain call's results. */
+typedef struct {
+  /* The per-chunk states the forward call kept (ttt_layer_options.W_states,
+   * [B, k, d, f] dtype, DEVICE, 16-byte aligned), or NULL: recomputed. */
+  const void* W_states;
+  /* Packed documents as in ttt_layer_options.doc_starts (each document is
+   * differentiated as the independent sequence the forward call makes of it),
+   * or NULL. */
+  const unsigned char* doc_starts;
+  /* The update mask of the forward call (ttt_layer_options.update_mask, [B, k]
+   * uint8, DEVICE), or NULL: every chunk updated.  A masked chunk is applied
+   * but adds nothing to the state, so its target gets no gradient (dVhat rows
+   * of the chunk are zero) and, for the MSE objective, its residual none. */
+  const unsigned char* update_mask;
+  /* The whole layer only: 1 when the forward call took the forward-looking
+   * in-chunk convolution (ttt_layer_options.conv_forward), 0 for the causal
+   * one; other values TTT_ERR_ARG. */
+  int conv_forward;
+} ttt_backward_options;
+
 /* ---- backward of the dot chunk loop ---- */
 
 /* Workspace bytes for ttt_core_backward, with the states given (saved_states
@@ -265,8 +288,8 @@ int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype,
  * restart from W_down0 at each start, each suffix S_c runs to the end of c's
  * document (the reversed scan restarts from zero where the forward order's
  * documents end), and dW_down0 receives every document's sum, formed by one
- * more contraction over all chunks (2 d f flop per token).  Resumed rows and
- * update masks are not handled.  Inputs as in
+ * more contraction over all chunks (2 d f flop per token).  Update masks:
+ * ttt_core_backward_ex; resumed rows are not handled.  Inputs as in
  * ttt_core_apply_update; conv_k is not used.  seq_len == 0 or batch == 0
  * gives dW_down0 = 0 and touches nothing else.  Errors as for every entry
  * point (a too small workspace: TTT_ERR_WORKSPACE). */
@@ -300,8 +323,8 @@ int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dt
  * two-contraction dZ kernel, and the MSE update seeded with G.  doc_starts
  * [B, k] (DEVICE, as ttt_layer_options.doc_starts; NULL: one document per
  * row) packs documents: at a document's first chunk G goes to dW_down0 and
- * restarts from zero for the chunk before.  Resumed rows and update masks
- * are not handled.
+ * restarts from zero for the chunk before.  Update masks:
+ * ttt_core_backward_ex; resumed rows are not handled.
  * seq_len == 0 or batch == 0 gives dW_down0 = 0.  Errors as for every entry
  * point. */
 int ttt_core_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
@@ -350,6 +373,17 @@ int ttt_layer_backward(const ttt_inplace_shape* shape, int dtype, float eta, con
                        void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
                        float* dconv_w, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The chunk loop's backward for either objective with options:
+ * mode TTT_MODE_DOT (or TTT_MODE_DOT_SCAN) as ttt_core_backward, TTT_MODE_MSE as
+ * ttt_core_backward_mse; W_states and doc_starts as there, update_mask as in
+ * ttt_backward_options (conv_forward is not read).  Workspace: the matching
+ * ttt_core_backward_workspace_bytes or ttt_core_backward_mse_workspace_bytes.
+ * Other arguments, rules and errors as for those calls. */
+int ttt_core_backward_ex(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* Z,
+                         const void* Vhat, const void* W_down0, const void* dO, const ttt_backward_options* options,
+                         void* dZ, void* dVhat, float* dW_down0, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* ---- backward of the whole MSE layer ---- */
 
 /* Workspace bytes for ttt_layer_backward_mse (saved_states as for
@@ -373,6 +407,21 @@ int ttt_layer_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta,
                            const void* conv_w, const void* dO, const void* W_states, const unsigned char* doc_starts,
                            void* dH, void* dX0, float* dW_gate, float* dW_up, float* dW_down0, float* dW_target,
                            float* dconv_w, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The whole layer's backward for either objective with options: mode
+ * TTT_MODE_DOT (or TTT_MODE_DOT_SCAN) as ttt_layer_backward, TTT_MODE_MSE as
+ * ttt_layer_backward_mse, and every field of ttt_backward_options (the update
+ * mask and the convolution's direction as the forward call took them; the
+ * forward-looking convolution's gradient stays inside each chunk, as its
+ * window does).  Workspace: ttt_layer_backward_workspace_bytes or
+ * ttt_layer_backward_mse_workspace_bytes.  Other arguments, rules and errors
+ * as for those calls. */
+int ttt_layer_backward_ex(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* H,
+                          const void* X0, const void* W_gate, const void* W_up, const void* W_down0,
+                          const void* W_target, const void* conv_w, const void* dO,
+                          const ttt_backward_options* options, void* dH, void* dX0, float* dW_gate, float* dW_up,
+                          float* dW_down0, float* dW_target, float* dconv_w, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /* ---- the individual steps (each is one stage of the call above; they compose
  *      into it and exist for composition and per-step checks).  The updates

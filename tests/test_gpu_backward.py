@@ -449,3 +449,56 @@ def test_mse_layer_backward_reduced_workload():
     torch.cuda.synchronize()
     for name, got, want in zip(GRAD_NAMES, grads, mse_layer_ref(cfg, x, dO)):
         assert rel(f64(got), want) < TOL["bf16"], name
+
+
+# ---------------------------------------------------------------- update masks and the forward conv
+
+@pytest.mark.parametrize("mode,dtype,C,k", [("dot", "f32", 96, 4), ("dot", "bf16", 128, 4), ("dot", "bf16", 72, 3),
+                                            ("mse", "f32", 96, 4), ("mse", "bf16", 128, 4)])
+def test_core_backward_with_update_mask(mode, dtype, C, k):
+    """The chunk loop's backward with an update mask (ttt_core_backward_ex): two rows with different masks, on the
+    fused scan with segments, the delta + scan path (chunk 72) and the MSE recursion; masked chunks' dVhat rows
+    exactly zero; the states the masked forward call keeps give the same results."""
+    cfg = cfg_of(dtype, 2, k, C, eta=0.05 if mode == "dot" else 0.5, seed=33).with_(mode=mode)
+    x = ti.backward_inputs(cfg)
+    g = {name: t.cuda() for name, t in x.items()}
+    mask = np.array([[1, 0, 1, 1][:k], [0, 1, 1, 0][:k]], dtype=np.uint8)
+    um = torch.from_numpy(mask).cuda()
+    fn = cw.ttt_core_backward if mode == "dot" else cw.ttt_core_backward_mse
+    got = fn(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta, update_mask=um)
+    Ws = torch.empty(2, k, cfg.d_model, cfg.d_ff, dtype=g["Z"].dtype, device="cuda")
+    cw.ttt_core_apply_update(g["Z"], g["Vhat"], g["W_down0"], C, cfg.eta, mode, W_states=Ws, update_mask=um)
+    kept = fn(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta, update_mask=um, W_states=Ws)
+    torch.cuda.synchronize()
+    Z, V, W0, dO = (ti.to_f64(x[name]) for name in ("Z", "Vhat", "W_down0", "dO"))
+    back = orc.chunk_core_backward if mode == "dot" else orc.mse_core_backward
+    outs = [back(Z[b], V[b], W0, C, cfg.eta, dO[b], update_mask=mask[b]) for b in range(2)]
+    ref = (np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]), sum(o[2] for o in outs))
+    for res in (got, kept):
+        for name, a, b in zip(("dZ", "dVhat", "dW_down0"), res, ref):
+            assert rel(f64(a), b) < TOL[dtype], name
+    for b in range(2):
+        for c in range(k):
+            if not mask[b, c]:
+                assert not torch.any(got[1][b, c * C:(c + 1) * C]), (b, c)
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_layer_backward_forward_conv_and_mask(mode, dtype):
+    """The whole layer's backward (ttt_layer_backward_ex) with the forward-looking in-chunk convolution and an
+    update mask, two rows with different masks, K = 4, ragged 264 x 392, four chunks."""
+    C = 128
+    cfg = ti.InplaceConfig("lbwdx", 2, 4 * C, 264, 392, C, 0.05 if mode == "dot" else 0.5, mode, dtype, seed=65)
+    x = ti.inplace_inputs(cfg)
+    dO = ti.backward_inputs(cfg.with_(seed=66))["dO"]
+    mask = np.array([[1, 0, 1, 1], [0, 1, 0, 1]], dtype=np.uint8)
+    g = {name: t.cuda() for name, t in x.items()}
+    grads = cw.ttt_layer_backward(*layer_args(g), dO.cuda(), C, cfg.eta, mode=mode,
+                                  update_mask=torch.from_numpy(mask).cuda(), conv_forward=True)
+    torch.cuda.synchronize()
+    ref = orc.layer_backward(*(ti.to_f64(x[name]) for name in ("H", "X0", "W_gate", "W_up", "W_down0", "W_target",
+                                                               "conv_w")), C, cfg.eta, ti.to_f64(dO), mode=mode,
+                             update_mask=mask, conv_forward=True)
+    for name, got, want in zip(GRAD_NAMES, grads, ref):
+        assert rel(f64(got), want) < TOL[dtype], name
