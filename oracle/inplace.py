@@ -47,7 +47,7 @@ __all__ = [
     "silu", "causal_depthwise_conv1d", "forward_chunk_conv1d", "target_values", "gated_intermediate",
     "gated_mlp", "loss_dot", "loss_mse", "grad_dot", "grad_mse",
     "chunk_apply_update", "chunk_core_backward", "mse_core_backward", "chunk_prefix_form", "inplace_layer",
-    "layer_backward",
+    "layer_backward", "resumed_core_backward",
 ]
 
 
@@ -272,6 +272,30 @@ def mse_core_backward(Z, Vhat, W0, chunk, eta, dO, doc_starts=None, update_mask=
     return dZ, dV, G
 
 
+def resumed_core_backward(Z, Vhat, W0, W_init, chunk, eta, dO, mode, doc_starts=None, update_mask=None):
+    """The chunk loop's backward for a resumed row (inplace_layer's W_init): its
+    first document continues from W_init unless doc_starts flags chunk 0, and
+    every later document starts from W0.  The documents are independent
+    sequences, so the first one's gradients are the plain backward with W_init
+    in place of W0, whose initial-state gradient is the row's dW_init.
+    Returns (dZ, dVhat, dW0, dW_init)."""
+    back = {"dot": chunk_core_backward, "mse": mse_core_backward}[mode]
+    n = len(Z)
+    k = -(-n // chunk)
+    flags = [bool(doc_starts[c]) if doc_starts is not None else False for c in range(k)]
+    if flags[0]:                                  # a document starts at the resume point: nothing continues
+        out = back(Z, Vhat, W0, chunk, eta, dO, doc_starts=doc_starts, update_mask=update_mask)
+        return out[0], out[1], out[2], np.zeros_like(_f64(W_init))
+    cut = next((c for c in range(1, k) if flags[c]), k)
+    e = min(cut * chunk, n)
+    um = lambda a, b: None if update_mask is None else update_mask[a:b]
+    first = back(Z[:e], Vhat[:e], W_init, chunk, eta, dO[:e], update_mask=um(0, cut))
+    if e == n:
+        return first[0], first[1], np.zeros_like(_f64(W0)), first[2]
+    rest = back(Z[e:], Vhat[e:], W0, chunk, eta, dO[e:], doc_starts=flags[cut:], update_mask=um(cut, k))
+    return (np.concatenate([first[0], rest[0]]), np.concatenate([first[1], rest[1]]), rest[2], first[2])
+
+
 def chunk_prefix_form(Z, Vhat, W0, chunk, eta):
     """The three-step parallel form of the dot-product update (Method §3):
     (1) every chunk's delta V^_c^T Z_c, (2) one exclusive prefix sum over the
@@ -365,7 +389,7 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
 
 
 def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, dO, doc_starts=None, mode="dot",
-                   update_mask=None, conv_forward=False):
+                   update_mask=None, conv_forward=False, W_init=None, x0_halo=None):
     """Gradients of a loss that depends on the output O of the layer
     (inplace_layer with the causal convolution, one document per row, and the
     objective `mode`, "dot" or "mse"), given dO = dLoss/dO [B, n, d].  Returns
@@ -401,7 +425,17 @@ def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, d
     dconv_w[i, j] = sum_t dY[t, i] X0[t + j, i] and
     dX0[s, i] = sum_j conv_w[i, j] dY[s - j, i], both over pairs inside one
     chunk.
+
+    `W_init` [B, d, f] and `x0_halo` [B, K-1, d] (either may be None) resume
+    rows as in inplace_layer: a row's first document continues from W_init
+    and reads the halo before its first token unless doc_starts flags chunk
+    0.  Then two more gradients are returned, dW_init [B, d, f] (the initial
+    states') and dx0_halo [B, K-1, d] (the halo rows'), both zero for rows
+    that start a document at chunk 0: the returned tuple has nine entries.
     """
+    if W_init is not None or x0_halo is not None:
+        return _resumed_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, dO, doc_starts,
+                                       mode, update_mask, conv_forward, W_init, x0_halo)
     if doc_starts is not None:
         outs = []
         for b in range(len(H)):
@@ -454,3 +488,86 @@ def layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, d
             dcw[:, j] += np.sum(dY[back:] * X0[b, : n - back], axis=0)
             dX0[b, : n - back] += cw[:, j] * dY[back:]
     return dH, dX0, dWg, dWu, dW0, dWt, dcw
+
+
+def _resumed_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta, dO, doc_starts, mode,
+                            update_mask, conv_forward, W_init, x0_halo):
+    """layer_backward for resumed rows (see there), one row at a time: a row
+    that starts a document at chunk 0 is the plain backward; otherwise its
+    first document is differentiated with the halo rows joined in front of
+    X0 (the causal convolution reads them) and W_init as the chunk loop's
+    initial state, and its later documents as independent rows."""
+    H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO = map(
+        _f64, (H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO))
+    B, n, d = H.shape
+    f, K = W_gate.shape[0], conv_w.shape[1]
+    k = -(-n // chunk) if n else 0
+    out = [np.zeros_like(H), np.zeros_like(X0), np.zeros_like(W_gate), np.zeros_like(W_up),
+           np.zeros_like(W_down0), np.zeros_like(W_target), np.zeros_like(conv_w),
+           np.zeros((B, d, f)), np.zeros((B, K - 1, d))]
+    for b in range(B):
+        flags = [bool(doc_starts[b][c]) if doc_starts is not None else False for c in range(k)]
+        um = None if update_mask is None else update_mask[b]
+        if k == 0:
+            continue
+        if flags[0]:
+            g = layer_backward(H[b:b + 1], X0[b:b + 1], W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
+                               dO[b:b + 1], doc_starts=[flags], mode=mode, update_mask=None if um is None else [um],
+                               conv_forward=conv_forward)
+            out[0][b], out[1][b] = g[0][0], g[1][0]
+            for i in range(2, 7):
+                out[i] += g[i]
+            continue
+        cut = next((c for c in range(1, k) if flags[c]), k)
+        e = min(cut * chunk, n)
+        # the first document: the halo in front of X0, W_init as the initial state
+        halo = np.zeros((K - 1, d)) if x0_halo is None else _f64(x0_halo[b])
+        Xf = np.concatenate([halo, X0[b, :e]])
+        Hb, dOb = H[b, :e], dO[b, :e]
+        A = Hb @ W_gate.T
+        U = Hb @ W_up.T
+        with np.errstate(over="ignore"):
+            sg = 1.0 / (1.0 + np.exp(-A))
+        Z = A * sg * U
+        if conv_forward:
+            Y = forward_chunk_conv1d(X0[b, :e], conv_w, chunk)
+        else:
+            Y = causal_depthwise_conv1d(Xf, conv_w)[K - 1:]
+        V = Y @ W_target
+        Wi = W_down0 if W_init is None else _f64(W_init[b])
+        back = {"dot": chunk_core_backward, "mse": mse_core_backward}[mode]
+        dZ, dV, dWi = back(Z, V, Wi, chunk, eta, dOb, update_mask=None if um is None else um[:cut])
+        if W_init is not None:
+            out[7][b] = dWi
+        else:
+            out[4] += dWi
+        dA = dZ * U * (sg * (1.0 + A * (1.0 - sg)))
+        dU = dZ * (A * sg)
+        out[2] += dA.T @ Hb
+        out[3] += dU.T @ Hb
+        out[0][b, :e] = dA @ W_gate + dU @ W_up
+        out[5] += Y.T @ dV
+        dY = dV @ W_target.T
+        if conv_forward:              # the window stays inside the chunk: the halo is never read
+            for s0 in range(0, e, chunk):
+                e0 = min(s0 + chunk, e)
+                for j in range(min(K, e0 - s0)):
+                    out[6][:, j] += np.sum(dY[s0: e0 - j] * X0[b, s0 + j: e0], axis=0)
+                    out[1][b, s0 + j: e0] += conv_w[:, j] * dY[s0: e0 - j]
+        else:                         # over the joined rows: row r of Xf is position r - (K-1)
+            dXf = np.zeros_like(Xf)
+            for j in range(K):
+                out[6][:, j] += np.sum(dY * Xf[j: j + e], axis=0)
+                dXf[j: j + e] += conv_w[:, j] * dY
+            out[1][b, :e] = dXf[K - 1:]
+            if x0_halo is not None:
+                out[8][b] = dXf[:K - 1]
+        if e < n:                     # the later documents: independent rows
+            g = layer_backward(H[b:b + 1, e:], X0[b:b + 1, e:], W_gate, W_up, W_down0, W_target, conv_w, chunk,
+                               eta, dO[b:b + 1, e:], doc_starts=[flags[cut:]], mode=mode,
+                               update_mask=None if um is None else [um[cut:]], conv_forward=conv_forward)
+            out[0][b, e:] = g[0][0]
+            out[1][b, e:] = g[1][0]
+            for i in range(2, 7):
+                out[i] += g[i]
+    return tuple(out)

@@ -912,3 +912,96 @@ def test_layer_backward_forward_conv_and_mask_match_autograd(mode):
         np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-10, atol=1e-11)
     O, _ = orc.inplace_layer(*args, C, eta, mode, update_mask=mask, conv_forward=True)
     np.testing.assert_allclose(O, torch.stack(rows).detach().numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- backward of resumed rows
+
+def _torch_resumed_layer(ts, C, eta, mode, docs, mask, conv_forward):
+    """The layer over resumed rows written per document in torch float64: a row's documents are cut at its flagged
+    chunks; the first one continues (reads the halo, starts from W_init) unless chunk 0 is flagged; every other
+    document starts from W_down0 with zeros before its first row."""
+    import torch.nn.functional as F
+    H, X0, Wg, Wu, W0, Wt, cw, Wi, halo = ts
+    B, n, d = H.shape
+    K = cw.shape[1]
+    k = -(-n // C)
+    rows = []
+    for b in range(B):
+        starts = [0] + [c for c in range(1, k) if docs[b][c]] + [k]
+        outs = []
+        for j in range(len(starts) - 1):
+            s, e = starts[j] * C, min(starts[j + 1] * C, n)
+            cont = j == 0 and not docs[b][0]
+            Z = F.silu(H[b, s:e] @ Wg.T) * (H[b, s:e] @ Wu.T)
+            if conv_forward:
+                Y = torch.cat([F.conv1d(F.pad(X0[b, t:min(t + C, e)].T[None], (0, K - 1)), cw[:, None, :],
+                                        groups=d)[0].T for t in range(s, e, C)])
+            else:
+                pre = halo[b] if (cont and halo is not None) else torch.zeros(K - 1, d, dtype=H.dtype)
+                Y = F.conv1d(torch.cat([pre, X0[b, s:e]]).T[None], cw[:, None, :], groups=d)[0].T
+            Ws = Wi[b] if (cont and Wi is not None) else W0
+            m = [1] * (e // C + 1) if mask is None else mask[b]
+            outs.append(_torch_loop(Z, Y @ Wt, Ws, C, eta, mode, m[starts[j]:]))
+        rows.append(torch.cat(outs))
+    return torch.stack(rows)
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+@pytest.mark.parametrize("case", ["both", "state_only", "halo_only", "mask", "forward_conv"])
+def test_layer_backward_resumed_rows_match_autograd(mode, case):
+    """Resumed rows (W_init and the halo of the previous call's last K-1 rows), three rows: one continuing with a
+    second document at chunk 2, one flagged at chunk 0 (nothing continues: zero dW_init and dx0_halo), one
+    continuing to its end.  Every gradient, dW_init and dx0_halo included, against autograd of the per-document
+    torch layer, whose output is also the oracle's forward."""
+    rng = _rng(60)
+    B, n, C, d, f, K, eta = 3, 14, 4, 3, 4, 3, 0.3
+    shapes = ((B, n, d), (B, n, d), (f, d), (f, d), (d, f), (d, d), (d, K), (B, d, f), (B, K - 1, d))
+    args = [rng.standard_normal(sh) * 0.7 for sh in shapes]
+    dO = rng.standard_normal((B, n, d))
+    docs = np.array([[0, 0, 1, 0], [1, 0, 0, 1], [0, 0, 0, 0]])
+    mask = np.array([[1, 0, 1, 1], [0, 1, 1, 1], [1, 1, 0, 1]]) if case == "mask" else None
+    if case == "state_only":
+        args[8] = None
+    if case == "halo_only":
+        args[7] = None
+    fwd = case == "forward_conv"
+    ours = orc.layer_backward(*args[:7], C, eta, dO, doc_starts=docs, mode=mode, update_mask=mask,
+                              conv_forward=fwd, W_init=args[7], x0_halo=args[8])
+    assert len(ours) == 9
+    ts = [None if a is None else torch.tensor(a, requires_grad=True) for a in args]
+    O = _torch_resumed_layer(ts, C, eta, mode, docs, mask, fwd)
+    (O * torch.from_numpy(dO)).sum().backward()
+    for i, t in enumerate(ts):
+        want = np.zeros_like(ours[i]) if t is None or t.grad is None else t.grad.numpy()
+        np.testing.assert_allclose(ours[i], want, rtol=1e-10, atol=1e-11, err_msg=f"gradient {i}")
+    assert not ours[7][1].any() and not ours[8][1].any()
+    if fwd:
+        assert not ours[8].any()
+    Of, _ = orc.inplace_layer(*args[:7], C, eta, mode, x0_halo=args[8], doc_starts=docs, conv_forward=fwd,
+                              W_init=args[7], update_mask=mask)
+    np.testing.assert_allclose(Of, O.detach().numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_resumed_core_backward_matches_autograd(mode):
+    """The chunk loop of a resumed row with a second document at chunk 3: autograd of the two documents (the first
+    from W_init, the second from W_down0) gives dZ, dV^, dW_down0 (second document only) and dW_init (first only);
+    a row flagged at chunk 0 is the plain backward with a zero dW_init."""
+    rng = _rng(61)
+    n, C, d, f, eta = 17, 3, 3, 4, 0.35
+    Z, V, W0, Wi, dO = (rng.standard_normal(sh) for sh in ((n, f), (n, d), (d, f), (d, f), (n, d)))
+    docs = [0, 0, 0, 1, 0, 0]
+    ours = orc.resumed_core_backward(Z, V, W0, Wi, C, eta, dO, mode, doc_starts=docs)
+    tz, tv, tw, ti = (torch.tensor(a, requires_grad=True) for a in (Z, V, W0, Wi))
+    ones = [1] * 6
+    O = torch.cat([_torch_loop(tz[:9], tv[:9], ti, C, eta, mode, ones), _torch_loop(tz[9:], tv[9:], tw, C, eta,
+                                                                                   mode, ones)])
+    (O * torch.from_numpy(dO)).sum().backward()
+    for got, t in zip(ours, (tz, tv, tw, ti)):
+        np.testing.assert_allclose(got, t.grad.numpy(), rtol=1e-11, atol=1e-12)
+    back = orc.chunk_core_backward if mode == "dot" else orc.mse_core_backward
+    flagged = [1, 0, 0, 1, 0, 0]
+    r = orc.resumed_core_backward(Z, V, W0, Wi, C, eta, dO, mode, doc_starts=flagged)
+    for a, b in zip(r[:3], back(Z, V, W0, C, eta, dO, doc_starts=flagged)):
+        np.testing.assert_array_equal(a, b)
+    assert not r[3].any()
