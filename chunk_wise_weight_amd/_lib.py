@@ -62,7 +62,8 @@ class LactSideStream:
 
 class BackwardOptions(ctypes.Structure):
     _fields_ = [("W_states", ctypes.c_void_p), ("doc_starts", ctypes.c_void_p), ("update_mask", ctypes.c_void_p),
-                ("conv_forward", ctypes.c_int)]
+                ("conv_forward", ctypes.c_int), ("W_init", ctypes.c_void_p), ("x0_halo", ctypes.c_void_p),
+                ("dW_init", ctypes.c_void_p), ("dx0_halo", ctypes.c_void_p)]
 
 
 class LactShape(ctypes.Structure):
@@ -160,6 +161,11 @@ def _dt(dtype: torch.dtype) -> int:
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _vp(t):
+    """A tensor's address, or None for a missing or empty tensor."""
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else None
 
 
 def _stream(device: torch.device):
@@ -295,10 +301,10 @@ def ttt_chunk_apply_update_noalloc(H, X0, W_gate, W_up, W_down0, W_target, conv_
 
 
 def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", O=None, W_final=None,
-                          workspace=None, W_states=None, update_mask=None, doc_starts=None):
+                          workspace=None, W_states=None, update_mask=None, doc_starts=None, W_init=None):
     """The chunk loop given Z [B, n, f] and Vhat [B, n, d].  Returns (O, W_final).  W_states [B, n // chunk, d, f]
-    (dtype), if given, receives the per-chunk states; update_mask and doc_starts [B, n // chunk] as for the layer
-    (all through ttt_core_apply_update_ex)."""
+    (dtype), if given, receives the per-chunk states; update_mask and doc_starts [B, n // chunk] and W_init
+    [B, d, f] fp32 as for the layer (all through ttt_core_apply_update_ex)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
     dt, dev = Z.dtype, Z.device
@@ -314,11 +320,12 @@ def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", 
     ws = _workspace(nbytes, dev, workspace)
     update_mask = _flags(update_mask, "update_mask", (B, n // chunk if chunk > 0 else 0), dev)
     doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
-    if W_states is not None or update_mask is not None or doc_starts is not None:
+    if W_states is not None or update_mask is not None or doc_starts is not None or W_init is not None:
         if W_states is not None:
             _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
-        ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
-        opts = LayerOptions(ptr(doc_starts), 0, None, None, ptr(W_states), ptr(update_mask))
+        if W_init is not None:
+            _need(W_init, "W_init", (B, d, f), torch.float32, dev)
+        opts = LayerOptions(_vp(doc_starts), 0, _vp(W_init), None, _vp(W_states), _vp(update_mask))
         _check(lib().ttt_core_apply_update_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(Z),
                                               _ptr(Vhat), _ptr(W_down0), ctypes.byref(opts), _ptr(O), _ptr(W_final),
                                               _ptr(ws), nbytes, _stream(dev)),
@@ -338,22 +345,8 @@ def ttt_core_backward_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, s
     return n.value
 
 
-def _core_backward_ex(mode, shape, dt, eta, Z, Vhat, W_down0, dO, sp, dp, update_mask, dZ, dVhat, dW_down0, ws,
-                      nbytes, dev):
-    um = _flags(update_mask, "update_mask", (shape.batch, shape.seq_len // shape.chunk if shape.chunk > 0 else 0),
-                dev)
-    opts = BackwardOptions(sp, dp, ctypes.c_void_p(um.data_ptr()) if um.numel() else None, 0)
-    _check(lib().ttt_core_backward_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(Z), _ptr(Vhat),
-                                      _ptr(W_down0), _ptr(dO), ctypes.byref(opts), _ptr(dZ), _ptr(dVhat),
-                                      _ptr(dW_down0), _ptr(ws), nbytes, _stream(dev)), "ttt_core_backward_ex")
-
-
-def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVhat=None, dW_down0=None,
-                      workspace=None, W_states=None, doc_starts=None, update_mask=None):
-    """Gradients through the dot chunk loop given dO = dLoss/dO [B, n, d], with the per-chunk states W_states
-    [B, n // chunk, d, f] kept by the forward call, or recomputed (None); doc_starts [B, n // chunk] packs documents
-    and update_mask [B, n // chunk] masks updates as for the forward layer (the mask through ttt_core_backward_ex).
-    Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
+def _core_backward(mode, Z, Vhat, W_down0, dO, chunk, eta, dZ, dVhat, dW_down0, workspace, W_states, doc_starts,
+                   update_mask, W_init):
     B, n, f = Z.shape
     d = Vhat.shape[2]
     dt, dev = Z.dtype, Z.device
@@ -368,22 +361,42 @@ def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVh
     _need(dZ, "dZ", (B, n, f), dt, dev)
     _need(dVhat, "dVhat", (B, n, d), dt, dev)
     _need(dW_down0, "dW_down0", (d, f), torch.float32, dev)
+    k = n // chunk if chunk > 0 else 0
     if W_states is not None:
-        _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
-    nbytes = ttt_core_backward_workspace_bytes(shape, dt, W_states is not None)
+        _need(W_states, "W_states", (B, k, d, f), dt, dev)
+    dW_init = None
+    if W_init is not None:
+        _need(W_init, "W_init", (B, d, f), torch.float32, dev)
+        dW_init = torch.empty(B, d, f, dtype=torch.float32, device=dev)
+    nbytes = (ttt_core_backward_mse_workspace_bytes if mode == "mse" else ttt_core_backward_workspace_bytes)(
+        shape, dt, W_states is not None)
     ws = _workspace(nbytes, dev, workspace)
-    sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
-    doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
-    dp = ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None and doc_starts.numel() else None
-    if update_mask is not None:
-        _core_backward_ex("dot", shape, dt, eta, Z, Vhat, W_down0, dO, sp, dp, update_mask, dZ, dVhat, dW_down0, ws,
-                          nbytes, dev)
-        return dZ, dVhat, dW_down0
-    _check(lib().ttt_core_backward(ctypes.byref(shape), _dt(dt), float(eta), _ptr(Z), _ptr(Vhat), _ptr(W_down0),
-                                   _ptr(dO), sp, dp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
-                                   _stream(dev)),
-           "ttt_core_backward")
-    return dZ, dVhat, dW_down0
+    sp = _vp(W_states)
+    doc_starts = _flags(doc_starts, "doc_starts", (B, k), dev)
+    dp = _vp(doc_starts)
+    if update_mask is not None or W_init is not None:
+        um = _flags(update_mask, "update_mask", (B, k), dev)
+        opts = BackwardOptions(sp, dp, _vp(um), 0, _vp(W_init), None, _vp(dW_init), None)
+        _check(lib().ttt_core_backward_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(Z), _ptr(Vhat),
+                                          _ptr(W_down0), _ptr(dO), ctypes.byref(opts), _ptr(dZ), _ptr(dVhat),
+                                          _ptr(dW_down0), _ptr(ws), nbytes, _stream(dev)), "ttt_core_backward_ex")
+    else:
+        name = "ttt_core_backward_mse" if mode == "mse" else "ttt_core_backward"
+        _check(getattr(lib(), name)(ctypes.byref(shape), _dt(dt), float(eta), _ptr(Z), _ptr(Vhat), _ptr(W_down0),
+                                    _ptr(dO), sp, dp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
+                                    _stream(dev)), name)
+    return (dZ, dVhat, dW_down0) if W_init is None else (dZ, dVhat, dW_down0, dW_init)
+
+
+def ttt_core_backward(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVhat=None, dW_down0=None,
+                      workspace=None, W_states=None, doc_starts=None, update_mask=None, W_init=None):
+    """Gradients through the dot chunk loop given dO = dLoss/dO [B, n, d], with the per-chunk states W_states
+    [B, n // chunk, d, f] kept by the forward call, or recomputed (None); doc_starts [B, n // chunk] packs documents,
+    update_mask [B, n // chunk] masks updates and W_init [B, d, f] fp32 resumes rows as for the forward layer (the
+    last two through ttt_core_backward_ex).  Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32), and
+    dW_init [B, d, f] fp32 after them when W_init is given."""
+    return _core_backward("dot", Z, Vhat, W_down0, dO, chunk, eta, dZ, dVhat, dW_down0, workspace, W_states,
+                          doc_starts, update_mask, W_init)
 
 
 def ttt_core_backward_mse_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, saved_states=False) -> int:
@@ -395,41 +408,10 @@ def ttt_core_backward_mse_workspace_bytes(shape: InplaceShape, dtype: torch.dtyp
 
 
 def ttt_core_backward_mse(Z, Vhat, W_down0, dO, chunk: int, eta: float, dZ=None, dVhat=None, dW_down0=None,
-                          workspace=None, W_states=None, doc_starts=None, update_mask=None):
-    """Gradients through the MSE chunk loop given dO = dLoss/dO [B, n, d], with the per-chunk states W_states
-    [B, n // chunk, d, f] kept by the forward call, or recomputed (None); doc_starts [B, n // chunk] packs documents
-    and update_mask [B, n // chunk] masks updates as for the forward layer (the mask through ttt_core_backward_ex).
-    Returns (dZ [B, n, f], dVhat [B, n, d], dW_down0 [d, f] fp32)."""
-    B, n, f = Z.shape
-    d = Vhat.shape[2]
-    dt, dev = Z.dtype, Z.device
-    _need(Z, "Z", (B, n, f), dt, dev)
-    _need(Vhat, "Vhat", (B, n, d), dt, dev)
-    _need(W_down0, "W_down0", (d, f), dt, dev)
-    _need(dO, "dO", (B, n, d), dt, dev)
-    shape = _inplace_shape(B, n, d, f, chunk, 1)
-    dZ = torch.empty(B, n, f, dtype=dt, device=dev) if dZ is None else dZ
-    dVhat = torch.empty(B, n, d, dtype=dt, device=dev) if dVhat is None else dVhat
-    dW_down0 = torch.empty(d, f, dtype=torch.float32, device=dev) if dW_down0 is None else dW_down0
-    _need(dZ, "dZ", (B, n, f), dt, dev)
-    _need(dVhat, "dVhat", (B, n, d), dt, dev)
-    _need(dW_down0, "dW_down0", (d, f), torch.float32, dev)
-    if W_states is not None:
-        _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
-    nbytes = ttt_core_backward_mse_workspace_bytes(shape, dt, W_states is not None)
-    ws = _workspace(nbytes, dev, workspace)
-    sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
-    doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
-    dp = ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None and doc_starts.numel() else None
-    if update_mask is not None:
-        _core_backward_ex("mse", shape, dt, eta, Z, Vhat, W_down0, dO, sp, dp, update_mask, dZ, dVhat, dW_down0, ws,
-                          nbytes, dev)
-        return dZ, dVhat, dW_down0
-    _check(lib().ttt_core_backward_mse(ctypes.byref(shape), _dt(dt), float(eta), _ptr(Z), _ptr(Vhat), _ptr(W_down0),
-                                       _ptr(dO), sp, dp, _ptr(dZ), _ptr(dVhat), _ptr(dW_down0), _ptr(ws), nbytes,
-                                       _stream(dev)),
-           "ttt_core_backward_mse")
-    return dZ, dVhat, dW_down0
+                          workspace=None, W_states=None, doc_starts=None, update_mask=None, W_init=None):
+    """ttt_core_backward for the MSE chunk loop (same arguments and results)."""
+    return _core_backward("mse", Z, Vhat, W_down0, dO, chunk, eta, dZ, dVhat, dW_down0, workspace, W_states,
+                          doc_starts, update_mask, W_init)
 
 
 def ttt_layer_backward_workspace_bytes(shape: InplaceShape, dtype: torch.dtype, saved_states=False,
@@ -453,12 +435,15 @@ def ttt_layer_backward_mse(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, c
 
 
 def ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk: int, eta: float, W_states=None,
-                       grads=None, workspace=None, doc_starts=None, mode="dot", update_mask=None, conv_forward=False):
+                       grads=None, workspace=None, doc_starts=None, mode="dot", update_mask=None, conv_forward=False,
+                       W_init=None, x0_halo=None):
     """Gradients of the layer (objective `mode`, "dot" or "mse") with respect to every input, given
     dO = dLoss/dO [B, n, d], with the per-chunk states W_states kept by the forward call or recomputed (None), and
-    doc_starts [B, n // chunk], update_mask [B, n // chunk] and conv_forward as the forward layer took them (the
-    last two through ttt_layer_backward_ex).  Returns (dH, dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w):
-    activations in the inputs' dtype, weight gradients fp32 summed over the batch rows."""
+    doc_starts [B, n // chunk], update_mask [B, n // chunk], conv_forward and the resumed rows' W_init [B, d, f]
+    fp32 and x0_halo [B, K-1, d] as the forward layer took them (all but the first through ttt_layer_backward_ex).
+    Returns (dH, dX0, dW_gate, dW_up, dW_down0, dW_target, dconv_w): activations in the inputs' dtype, weight
+    gradients fp32 summed over the batch rows; with W_init or x0_halo given, dW_init [B, d, f] fp32 and dx0_halo
+    [B, K-1, d] follow (None for the one not given)."""
     if mode not in ("dot", "mse"):
         raise ValueError(f"mode must be 'dot' or 'mse', got {mode!r}")
     B, n, d = H.shape
@@ -477,21 +462,30 @@ def ttt_layer_backward(H, X0, W_gate, W_up, W_down0, W_target, conv_w, dO, chunk
         _need(g, "gradient", shp, t, dev)
     if W_states is not None:
         _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
+    resumed = W_init is not None or x0_halo is not None
+    dW_init = dx0_halo = None
+    if W_init is not None:
+        _need(W_init, "W_init", (B, d, f), torch.float32, dev)
+        dW_init = torch.empty(B, d, f, dtype=torch.float32, device=dev)
+    if x0_halo is not None:
+        _need(x0_halo, "x0_halo", (B, K - 1, d), dt, dev)
+        dx0_halo = torch.empty(B, K - 1, d, dtype=dt, device=dev)
     shape = _inplace_shape(B, n, d, f, chunk, K)
     nbytes = ttt_layer_backward_workspace_bytes(shape, dt, W_states is not None, mode)
     ws = _workspace(nbytes, dev, workspace)
-    sp = ctypes.c_void_p(W_states.data_ptr()) if W_states is not None and W_states.numel() else None
+    sp = _vp(W_states)
     doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
-    dp = ctypes.c_void_p(doc_starts.data_ptr()) if doc_starts is not None and doc_starts.numel() else None
-    if update_mask is not None or conv_forward:
+    dp = _vp(doc_starts)
+    if update_mask is not None or conv_forward or resumed:
         um = _flags(update_mask, "update_mask", (B, n // chunk if chunk > 0 else 0), dev)
-        opts = BackwardOptions(sp, dp, ctypes.c_void_p(um.data_ptr()) if um is not None and um.numel() else None,
-                               1 if conv_forward else 0)
+        halo_ok = x0_halo is not None and K > 1
+        opts = BackwardOptions(sp, dp, _vp(um), 1 if conv_forward else 0, _vp(W_init),
+                               _vp(x0_halo) if halo_ok else None, _vp(dW_init), _vp(dx0_halo) if halo_ok else None)
         _check(lib().ttt_layer_backward_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H), _ptr(X0),
                                            _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target), _ptr(conv_w),
                                            _ptr(dO), ctypes.byref(opts), *[_ptr(g) for g in grads], _ptr(ws),
                                            nbytes, _stream(dev)), "ttt_layer_backward_ex")
-        return grads
+        return tuple(grads) + (dW_init, dx0_halo) if resumed else grads
     name = "ttt_layer_backward_mse" if mode == "mse" else "ttt_layer_backward"
     _check(getattr(lib(), name)(ctypes.byref(shape), _dt(dt), float(eta), _ptr(H), _ptr(X0), _ptr(W_gate),
                                 _ptr(W_up), _ptr(W_down0), _ptr(W_target), _ptr(conv_w), _ptr(dO), sp, dp,

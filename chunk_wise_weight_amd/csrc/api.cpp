@@ -267,6 +267,8 @@ struct BwdPlan {
   bool saved;         // the states come from the caller
   const uint8_t* docs;  // document starts [B, k] (device) or null
   const uint8_t* umask; // update mask [B, k] (device) or null: every chunk updates
+  const float* Winit;   // resumed rows: the initial states [B, d, f] fp32, or null
+  float* dWi;           // their gradient [B, d, f] fp32 (with Winit)
   int S;
   size_t off_Zt, off_Vt, off_Vs, off_Zr, off_Gr, off_Wc, off_Sr, off_T, off_zero, off_Wp, off_Tot, off_dW, off_rd,
       total;
@@ -321,27 +323,34 @@ int make_bwd_plan(const ttt_inplace_shape* s, int dtype, bool saved, BwdPlan* p,
 // token-contiguous copies (in the order wanted) and a scan with eta.
 template <typename T>
 int bwd_scan(const BwdPlan& p, const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, float eta, bool rev,
-             char* ws, hipStream_t s, const uint8_t* docs = nullptr) {
+             char* ws, hipStream_t s, const uint8_t* docs = nullptr, const float* Winit = nullptr) {
   const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
   if (p.fused)
     return dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (T*)(ws + p.off_Wp), (float*)(ws + p.off_Tot), B,
-                                                n, d, f, C, p.S, docs, nullptr, s,
+                                                n, d, f, C, p.S, docs, Winit, s,
                                                 rev ? ttt::kScanRowMajorReversed : ttt::kScanRowMajor));
   float* dW = (float*)(ws + p.off_dW);
   int st = dev(ttt::launch_chunk_delta<T>(Zt, Vt, dW, B, n, d, f, C, s));
-  if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, (int64_t)d * f, eta, docs, nullptr, s));
+  if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, (int64_t)d * f, eta, docs, Winit, s));
   return st;
 }
 
 // The backward pass: both scans, then dV^ as an apply of the suffix states (in
 // reverse chunk order, by a negative state stride) and dZ from both state
-// sequences, and dW_down0 as the sum of the rows' totals.
+// sequences, and dW_down0 as the sum of the rows' totals.  Resumed rows
+// (p.Winit): the states start from W_init, and the reversed scan's totals --
+// each row's first-document gradient -- are the rows' dW_init, taken off
+// dW_down0 where the row continues.
 template <typename T>
 int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, const void* W0, const void* dOv,
                   const void* Wsaved, void* dZ, void* dV, float* dW0, char* ws, hipStream_t s, bool vs_ready = false) {
   const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
   const int64_t df = (int64_t)d * f;
-  if (p.B * p.n == 0) return dev(ttt::launch_zero<float>(dW0, df, s));
+  if (p.B * p.n == 0) {
+    int st = dev(ttt::launch_zero<float>(dW0, df, s));
+    if (st == TTT_OK && p.Winit != nullptr) st = dev(ttt::launch_zero<float>(p.dWi, p.B * df, s));
+    return st;
+  }
   const T* Z = (const T*)Zv;
   const T* V = (const T*)Vv;
   const T* dO = (const T*)dOv;
@@ -362,7 +371,8 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
   if (st == TTT_OK && rd != nullptr) st = dev(ttt::launch_rev_docs(p.docs, (uint8_t*)rd, B, k, s));
   if (p.fused) {
     // W_c (its W_final lands in Tt and is overwritten by the scans after it)
-    if (st == TTT_OK && !p.saved) st = bwd_scan<T>(p, Z, Vs, (const T*)W0, Wc, Tt, eta, false, ws, s, p.docs);
+    if (st == TTT_OK && !p.saved)
+      st = bwd_scan<T>(p, Z, Vs, (const T*)W0, Wc, Tt, eta, false, ws, s, p.docs, p.Winit);
     if (st == TTT_OK && rd != nullptr) {
       st = bwd_scan<T>(p, Z, dO, Z0, Sr, Tt, 1.0f, false, ws, s);
       if (st == TTT_OK) st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
@@ -380,7 +390,8 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
     if (st == TTT_OK && !p.saved) st = dev(ttt::launch_transpose<T>(V, Vt, B, n, d, 1.0f, 0, s, p.umask, C));
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Z, Zr, B, n, f, 1.0f, C, s));
     if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(dO, Gr, B, n, d, 1.0f, C, s));
-    if (st == TTT_OK && !p.saved) st = bwd_scan<T>(p, Zt, Vt, (const T*)W0, Wc, Tt, eta, false, ws, s, p.docs);
+    if (st == TTT_OK && !p.saved)
+      st = bwd_scan<T>(p, Zt, Vt, (const T*)W0, Wc, Tt, eta, false, ws, s, p.docs, p.Winit);
     if (st == TTT_OK && rd != nullptr) {
       st = bwd_scan<T>(p, Zr, Gr, Z0, Sr, Tt, 1.0f, true, ws, s);
       if (st == TTT_OK) st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
@@ -394,7 +405,10 @@ int core_backward(const BwdPlan& p, float eta, const void* Zv, const void* Vv, c
   if (st == TTT_OK)
     st = dev(ttt::launch_dz<T>(dO, Vs, Wc, (int64_t)k * df, df, Slast, (int64_t)k * df, -df, (T*)dZ, B, n, d, f, C,
                                s));
-  if (st == TTT_OK && rd == nullptr) st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
+  if (st == TTT_OK && p.Winit != nullptr)
+    st = dev(ttt::launch_resume_split(Tt, p.docs, dW0, p.dWi, B, k, df, rd != nullptr, s));
+  else if (st == TTT_OK && rd == nullptr)
+    st = dev(ttt::launch_sum_rows(Tt, dW0, B, df, s));
   return st;
 }
 
@@ -411,6 +425,8 @@ struct MsePlan {
   size_t esz;
   const uint8_t* docs;  // document starts [B, k] (device) or null
   const uint8_t* umask; // update mask [B, k] (device) or null
+  const float* Winit;   // resumed rows: the initial states [B, d, f] fp32, or null
+  float* dWi;           // their gradient [B, d, f] fp32 (with Winit)
   size_t off_Vt, off_Gt, off_St, off_Ws, off_Wsh, off_G, off_Gsh, off_Rt, off_Tt, total;
 };
 
@@ -454,7 +470,12 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
                  const void* Wsaved, void* dZv, void* dVv, float* dW0, char* ws, hipStream_t s) {
   const int B = (int)p.B, n = (int)p.n, d = (int)p.d, f = (int)p.f, C = (int)p.C, k = (int)p.k;
   const int64_t df = (int64_t)d * f;
-  if (p.B * p.n == 0) return dev(ttt::launch_zero<float>(dW0, df, s));
+  const bool resume = p.Winit != nullptr;
+  if (p.B * p.n == 0) {
+    int st = dev(ttt::launch_zero<float>(dW0, df, s));
+    if (st == TTT_OK && resume) st = dev(ttt::launch_zero<float>(p.dWi, p.B * df, s));
+    return st;
+  }
   const bool bf = sizeof(T) == 2;
   const T* W0 = (const T*)W0v;
   const T* Zt = (const T*)Zv;           // Z [B, n, f] as it is (the kernels' row-major operand forms)
@@ -473,18 +494,20 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
   int st = dev(ttt::launch_transpose<T>((const T*)Vv, Vt, B, n, d, 1.0f, 0, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>((const T*)dOv, Gt, B, n, d, 1.0f, 0, s));
   // the forward scan again, keeping in St [B, k, d, f] the state each chunk's apply reads (W_down0 at a document
-  // start), unless the forward call kept them the same way (Wsaved)
+  // start, W_init where a resumed row continues), unless the forward call kept them the same way (Wsaved)
+  if (st == TTT_OK && Wsaved == nullptr && resume) st = dev(ttt::launch_state_copy<T>(p.Winit, Ws, Wsh, B, df, s));
   for (int c = 0; c < k && st == TTT_OK && Wsaved == nullptr; ++c) {
-    st = dev(ttt::launch_keep_state<T>(W0, Wcur, St, p.docs, false, B, k, c, df, s));
+    st = dev(ttt::launch_keep_state<T>(W0, Wcur, St, p.docs, resume, B, k, c, df, s));
     if (st == TTT_OK)
-      st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Ws, Wsh, nullptr, Rt, p.docs, false, B, n, d, f, C, c, eta,
+      st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Ws, Wsh, nullptr, Rt, p.docs, resume, B, n, d, f, C, c, eta,
                                         s, p.umask, true));
   }
   // the state gradient G = dLoss/dW_{c+1}, zero after the last chunk, taken back chunk by chunk
   if (st == TTT_OK) st = dev(ttt::launch_zero<float>(G, (int64_t)B * df, s));
   if (st == TTT_OK && bf) st = dev(ttt::launch_zero<T>(Gsh, (int64_t)B * df, s));
-  // packed rows: every document's gradient is added into dW_down0 at its first chunk
-  if (st == TTT_OK && p.docs != nullptr) st = dev(ttt::launch_zero<float>(dW0, df, s));
+  // packed or resumed rows: every document's gradient is added into dW_down0 at its first chunk (a resumed row's
+  // first document's goes to dW_init instead)
+  if (st == TTT_OK && (p.docs != nullptr || resume)) st = dev(ttt::launch_zero<float>(dW0, df, s));
   const T* Sb = Wsaved != nullptr ? (const T*)Wsaved : (const T*)St;
   const int64_t wstride = (int64_t)k * df;
   for (int c = k - 1; c >= 0 && st == TTT_OK; --c) {
@@ -502,11 +525,11 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
     // G <- G + T_c^T Z_c = dLoss/dW_c
     if (st == TTT_OK) st = dev(ttt::launch_mse_update<T>(Zt, Tt, W0, G, Gsh, true, B, n, d, f, C, c, s));
     // packed rows: a document's first chunk hands its gradient to dW_down0, and the one before starts from zero
-    if (st == TTT_OK && p.docs != nullptr)
-      st = dev(ttt::launch_doc_grad_reset<T>(G, Gsh, dW0, p.docs, B, k, c, df, s));
+    if (st == TTT_OK && (p.docs != nullptr || (resume && c == 0)))
+      st = dev(ttt::launch_doc_grad_reset<T>(G, Gsh, dW0, p.docs, B, k, c, df, s, resume ? p.dWi : nullptr));
   }
-  // (with documents, chunk 0 starts every row's first one, so every gradient is in dW_down0 by now)
-  if (st == TTT_OK && p.docs == nullptr) st = dev(ttt::launch_sum_rows(G, dW0, B, df, s));
+  // (with documents, chunk 0 starts every row's first one, so every gradient is in dW_down0 or dW_init by now)
+  if (st == TTT_OK && p.docs == nullptr && !resume) st = dev(ttt::launch_sum_rows(G, dW0, B, df, s));
   return st;
 }
 
@@ -519,6 +542,8 @@ int mse_backward(const MsePlan& p, float eta, const void* Zv, const void* Vv, co
 struct LayerBwdPlan {
   int mode;                     // TTT_MODE_DOT or TTT_MODE_MSE: the chunk loop differentiated
   bool conv_fwd;                // the forward-looking in-chunk convolution for the target
+  const void* halo;             // resumed rows: X0's K-1 rows before the first token [B, K-1, d], or null
+  void* dhalo;                  // their gradient (with halo)
   BwdPlan core;                 // its backward, dot objective
   MsePlan mcore;                // its backward, MSE objective
   int64_t B, n, d, f, C, K;
@@ -599,12 +624,17 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
                    float* dcw, char* ws, hipStream_t s) {
   const int B = (int)L.B, n = (int)L.n, d = (int)L.d, f = (int)L.f, C = (int)L.C, K = (int)L.K;
   const int64_t rows = L.B * L.n, fd = (int64_t)f * d;
+  const bool mse = L.mode == TTT_MODE_MSE;
   if (rows == 0) {
     int st = dev(ttt::launch_zero<float>(dWg, fd, s));
     if (st == TTT_OK) st = dev(ttt::launch_zero<float>(dWu, fd, s));
     if (st == TTT_OK) st = dev(ttt::launch_zero<float>(dW0, fd, s));
     if (st == TTT_OK) st = dev(ttt::launch_zero<float>(dWt, (int64_t)d * d, s));
     if (st == TTT_OK) st = dev(ttt::launch_zero<float>(dcw, (int64_t)d * K, s));
+    const float* Wi = mse ? L.mcore.Winit : L.core.Winit;
+    if (st == TTT_OK && Wi != nullptr)
+      st = dev(ttt::launch_zero<float>(mse ? L.mcore.dWi : L.core.dWi, L.B * (int64_t)d * f, s));
+    if (st == TTT_OK && L.dhalo != nullptr) st = dev(ttt::launch_zero<T>((T*)L.dhalo, L.B * (K - 1) * (int64_t)d, s));
     return st;
   }
   const T* H = (const T*)Hv;
@@ -621,7 +651,6 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
   float* wWf = (float*)(ws + L.off_wWf);
   float* part = (float*)(ws + L.off_part);
   char* cws = ws + L.off_core;
-  const bool mse = L.mode == TTT_MODE_MSE;
   const uint8_t* docs = mse ? L.mcore.docs : L.core.docs;
   // the target as the chunk loop's backward takes it: eta V^ in the dot core's own buffer, V^ for MSE
   T* Vs = mse ? (T*)(ws + L.off_V) : (T*)(cws + L.core.off_Vs);
@@ -629,7 +658,8 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
   int st = dev(ttt::launch_zero<T>((T*)(ws + L.off_wzero), L.DFm, s));
   if (st == TTT_OK) st = dev(ttt::launch_produce_z<T>(H, Wg, Wu, Z, nullptr, rows, n, d, f, s));
   if (st == TTT_OK)
-    st = dev(ttt::launch_conv<T>((const T*)X0v, (const T*)cwv, Y, rows, n, d, K, docs, C, L.conv_fwd, nullptr, s));
+    st = dev(ttt::launch_conv<T>((const T*)X0v, (const T*)cwv, Y, rows, n, d, K, docs, C, L.conv_fwd,
+                                 (const T*)L.halo, s));
   if (st == TTT_OK) st = dev(ttt::launch_transpose<T>(Wt, WtT, 1, d, d, 1.0f, 0, s));
   if (st == TTT_OK) st = dev(ttt::launch_apply<T>(Y, WtT, 0, 0, Vs, B, n, d, d, C, mse ? 1.0f : eta, s, true));
   // the chunk loop: dZ, dV^ and dW_down0
@@ -649,7 +679,7 @@ int layer_backward(const LayerBwdPlan& L, float eta, const void* Hv, const void*
   if (st == TTT_OK) st = dev(ttt::launch_apply<T>(dV, Wt, 0, 0, dY, B, n, d, d, C, 1.0f, s, true));
   if (st == TTT_OK)
     st = dev(ttt::launch_conv_bwd<T>((const T*)X0v, (const T*)cwv, dY, (T*)dX0v, part, rows, n, d, K, s, docs, C,
-                                     L.conv_fwd));
+                                     L.conv_fwd, (const T*)L.halo, (T*)L.dhalo));
   if (st == TTT_OK) st = dev(ttt::launch_sum_rows(part, dcw, (int)L.npart, (int64_t)d * K, s));
   return st;
 }
@@ -879,6 +909,17 @@ int ttt_layer_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int d
 
 namespace {
 
+// The resumed rows' fields of backward options: each gradient goes with its
+// input (both present and 16-byte aligned, or both null; with no batch rows
+// nothing is read); halo: whether x0_halo / dx0_halo are read at all.
+bool resume_args_ok(const ttt_backward_options* o, bool rows, bool halo) {
+  if ((o->W_init == nullptr) != (o->dW_init == nullptr)) return false;
+  if (rows && o->W_init != nullptr && (!ok_ptr(o->W_init) || !ok_ptr(o->dW_init))) return false;
+  if (!halo) return true;
+  if ((o->x0_halo == nullptr) != (o->dx0_halo == nullptr)) return false;
+  return o->x0_halo == nullptr || (ok_ptr(o->x0_halo) && ok_ptr(o->dx0_halo));
+}
+
 // The whole layer's backward for either objective (the entry points below).
 int layer_backward_call(int mode, const ttt_inplace_shape* shape, int dtype, float eta, const void* H, const void* X0,
                         const void* W_gate, const void* W_up, const void* W_down0, const void* W_target,
@@ -895,8 +936,12 @@ int layer_backward_call(int mode, const ttt_inplace_shape* shape, int dtype, flo
   if (st != TTT_OK) return st;
   p.core.docs = p.mcore.docs = o->doc_starts;
   p.core.umask = p.mcore.umask = o->update_mask;
+  p.core.Winit = p.mcore.Winit = o->W_init;
+  p.core.dWi = p.mcore.dWi = o->dW_init;
   p.conv_fwd = o->conv_forward == 1;
-  if (!finite(eta)) return TTT_ERR_ARG;
+  p.halo = p.K > 1 ? o->x0_halo : nullptr;
+  p.dhalo = p.K > 1 ? o->dx0_halo : nullptr;
+  if (!finite(eta) || !resume_args_ok(o, p.B > 0, p.B > 0 && p.K > 1)) return TTT_ERR_ARG;
   if (!ok_ptr(dW_gate) || !ok_ptr(dW_up) || !ok_ptr(dW_down0) || !ok_ptr(dW_target) || !ok_ptr(dconv_w) ||
       (o->W_states != nullptr && !aligned16(o->W_states)))
     return TTT_ERR_ARG;
@@ -933,7 +978,11 @@ int core_backward_call(int mode, const ttt_inplace_shape* shape, int dtype, floa
   total = mode == TTT_MODE_MSE ? q.total : p.total;
   p.docs = q.docs = o->doc_starts;
   p.umask = q.umask = o->update_mask;
-  if (!finite(eta) || !ok_ptr(dW_down0) || (Ws != nullptr && !aligned16(Ws))) return TTT_ERR_ARG;
+  p.Winit = q.Winit = o->W_init;
+  p.dWi = q.dWi = o->dW_init;
+  if (!finite(eta) || !ok_ptr(dW_down0) || (Ws != nullptr && !aligned16(Ws)) ||
+      !resume_args_ok(o, (mode == TTT_MODE_MSE ? q.B : p.B) > 0, false))
+    return TTT_ERR_ARG;
   if (BN > 0 && (!ok_ptr(Z) || !ok_ptr(Vhat) || !ok_ptr(W_down0) || !ok_ptr(dO) || !ok_ptr(dZ) || !ok_ptr(dVhat)))
     return TTT_ERR_ARG;
   if (total > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < total))

@@ -124,20 +124,24 @@ __global__ __launch_bounds__(256) void k_conv(const T* __restrict__ X0, const T*
   }
 }
 
-// Backward of the causal convolution of k_conv (no halo):
+// Backward of the causal convolution of k_conv:
 // dX0[s, ch] = sum_j conv_w[ch, j] dY[s + (KW-1) - j, ch], rows past the end of
 // s's document zero; and dconv_w[ch, j] = sum_t dY[t, ch] X0[t - (KW-1) + j, ch],
-// rows before the start of t's document zero.  Documents start at chunk
-// boundaries and KW - 1 < C_, so a group's windows reach at most the next
-// chunk (dY) or the previous one (X0).  One thread: one 16-byte channel chunk
-// over kConvBwdGroups groups of kConvRows rows (each group inside one batch
-// row), writing its share of dconv_w to part [blocks, d, KW] (fp32), which a
-// row sum then reduces.
+// rows before the start of t's document zero -- or, for a resumed row's first
+// document, the halo's rows (halo [B, KW-1, d]), whose gradient
+// dhalo[b, h, ch] = sum_{j <= h} conv_w[ch, j] dY[h - j, ch] the group holding
+// the row's first token writes (zero where chunk 0 starts a document; dhalo
+// may be null).  Documents start at chunk boundaries and KW - 1 < C_, so a
+// group's windows reach at most the next chunk (dY) or the previous one (X0).
+// One thread: one 16-byte channel chunk over kConvBwdGroups groups of
+// kConvRows rows (each group inside one batch row), writing its share of
+// dconv_w to part [blocks, d, KW] (fp32), which a row sum then reduces.
 template <typename T, int KW, bool FWD>
 __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ X0, const T* __restrict__ cw,
                                                   const T* __restrict__ dY, T* __restrict__ dX0,
                                                   float* __restrict__ part, int64_t rows, int n, int d,
-                                                  const uint8_t* __restrict__ docs, int C_) {
+                                                  const uint8_t* __restrict__ docs, int C_,
+                                                  const T* __restrict__ halo, T* __restrict__ dhalo) {
   constexpr int V = Vec<T>::V, RW = kConvRows, NIN = RW + KW - 1;
   const int nchunk = d / V;
   const int64_t ngroups = rows / RW;
@@ -188,6 +192,9 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ X0, cons
     // FWD (Y[t] = sum_j w_j X0[t + j] inside t's chunk): gy[i] = dY row r0 - (KW-1) + i (zero before the
     // chunk's first row), xs[i] = X0 row r0 + i (zero from the next chunk on); a window never leaves the chunk,
     // so documents, which start at chunk boundaries, need nothing more.
+    // a resumed row's first group reads the halo before its first token (never with FWD)
+    const bool use_halo = !FWD && halo != nullptr && pos0 == 0 && !doc_start(docs, row, kc, 0, true);
+    const T* hrow = use_halo ? halo + (row * (KW - 1)) * (int64_t)d + ch : nullptr;
     u32x4 gy[NIN], xs[NIN];
 #pragma unroll
     for (int i = 0; i < NIN; ++i) {
@@ -199,7 +206,35 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ X0, cons
       } else {
         gy[i] = pos0 + i < hi ? *reinterpret_cast<const u32x4*>(dY + (r0 + i) * d + ch) : u32x4{0u, 0u, 0u, 0u};
         xs[i] = pos0 + i - (KW - 1) >= lo ? *reinterpret_cast<const u32x4*>(X0 + (r0 + i - (KW - 1)) * d + ch)
+                : use_halo && i < KW - 1  ? *reinterpret_cast<const u32x4*>(hrow + (int64_t)i * d)
                                           : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (KW > 1 && dhalo != nullptr && pos0 == 0) {
+      // halo row h sits at position h - (KW-1): output t reads it through tap j = h - t
+#pragma unroll
+      for (int h = 0; h < KW - 1; ++h) {
+        float o[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v] = 0.f;
+        if (use_halo) {
+#pragma unroll
+          for (int j = 0; j <= h; ++j) {
+            float y[V];
+            unpack(gy[h - j], y);
+#pragma unroll
+            for (int v = 0; v < V; ++v) o[v] = fmaf(w[v][j], y[v], o[v]);
+          }
+        }
+        u32x4 out;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = pack2_bf16(o[2 * e], o[2 * e + 1]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = __float_as_uint(o[e]);
+        }
+        *reinterpret_cast<u32x4*>(dhalo + (row * (KW - 1) + h) * (int64_t)d + ch) = out;
       }
     }
 #pragma unroll
@@ -973,12 +1008,18 @@ __global__ __launch_bounds__(256) void k_keep_state(const T* __restrict__ W0, co
 template <typename T>
 __global__ __launch_bounds__(256) void k_doc_grad_reset(float* __restrict__ G, T* __restrict__ Gsh,
                                                         float* __restrict__ dW0, const uint8_t* __restrict__ docs,
-                                                        int B, int k, int c, int64_t df) {
+                                                        int B, int k, int c, int64_t df, float* __restrict__ dWi) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= df) return;
   f32x4 a = load4(dW0 + e);
   bool any = false;
   for (int b = 0; b < B; ++b) {
+    if (dWi != nullptr && c == 0) {     // resumed rows: chunk 0 starts a document only where flagged
+      const bool cont = !doc_start(docs, b, k, 0, true);
+      const f32x4 g = load4(G + (int64_t)b * df + e);
+      store4(dWi + (int64_t)b * df + e, cont ? g[0] : 0.f, cont ? g[1] : 0.f, cont ? g[2] : 0.f, cont ? g[3] : 0.f);
+      if (cont) continue;
+    }
     if (!doc_start(docs, b, k, c)) continue;
     const int64_t o = (int64_t)b * df + e;
     a += load4(G + o);
@@ -987,6 +1028,27 @@ __global__ __launch_bounds__(256) void k_doc_grad_reset(float* __restrict__ G, T
     if (Gsh != nullptr) store4(Gsh + o, 0.f, 0.f, 0.f, 0.f);
   }
   if (any) store4(dW0 + e, a[0], a[1], a[2], a[3]);
+}
+
+// Dot backward of resumed rows: Tt [B, d, f] holds each row's first-document
+// gradient (the reversed scan's totals).  A row continues from W_init unless
+// chunk 0 is flagged: then dWi[b] = Tt[b] and its first document is no part of
+// dW_down0, so it is taken off the all-document sum already in dW0 (have_dW0;
+// without packed documents every row continues and dW0 = 0).  Rows flagged at
+// chunk 0 get dWi[b] = 0.
+__global__ __launch_bounds__(256) void k_resume_split(const float* __restrict__ Tt, const uint8_t* __restrict__ docs,
+                                                      float* __restrict__ dW0, float* __restrict__ dWi, int B, int k,
+                                                      int64_t df, bool have_dW0) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= df) return;
+  f32x4 a = have_dW0 ? load4(dW0 + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < B; ++b) {
+    const bool cont = !doc_start(docs, b, k, 0, true);
+    const f32x4 g = cont ? load4(Tt + (int64_t)b * df + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (have_dW0) a -= g;
+    store4(dWi + (int64_t)b * df + e, g[0], g[1], g[2], g[3]);
+  }
+  store4(dW0 + e, a[0], a[1], a[2], a[3]);
 }
 
 // dst = scale * src over n elements, four per thread (n % 4 == 0).  With an
@@ -1211,7 +1273,7 @@ hipError_t launch_conv(const T* X0, const T* cw, T* Y, int64_t rows, int n, int 
 
 template <typename T>
 hipError_t launch_conv_bwd(const T* X0, const T* cw, const T* dY, T* dX0, float* part, int64_t rows, int n, int d,
-                           int K, hipStream_t s, const uint8_t* docs, int C, bool fwd) {
+                           int K, hipStream_t s, const uint8_t* docs, int C, bool fwd, const T* halo, T* dhalo) {
   if (rows == 0) return hipSuccess;
   const int64_t threads = conv_bwd_partials(rows) * (d / Vec<T>::V);
   const dim3 g((unsigned)cdiv(threads, 256));
@@ -1219,9 +1281,9 @@ hipError_t launch_conv_bwd(const T* X0, const T* cw, const T* dY, T* dX0, float*
 #define TTT_KW(KW)                                                                                            \
   case KW:                                                                                                    \
     if (fwd)                                                                                                  \
-      k_conv_bwd<T, KW, true><<<g, 256, 0, s>>>(X0, cw, dY, dX0, part, rows, n, d, docs, C);                  \
+      k_conv_bwd<T, KW, true><<<g, 256, 0, s>>>(X0, cw, dY, dX0, part, rows, n, d, docs, C, nullptr, dhalo);  \
     else                                                                                                      \
-      k_conv_bwd<T, KW, false><<<g, 256, 0, s>>>(X0, cw, dY, dX0, part, rows, n, d, docs, C);                 \
+      k_conv_bwd<T, KW, false><<<g, 256, 0, s>>>(X0, cw, dY, dX0, part, rows, n, d, docs, C, halo, dhalo);    \
     break;
     TTT_KW(1) TTT_KW(2) TTT_KW(3) TTT_KW(4) TTT_KW(5) TTT_KW(6) TTT_KW(7) TTT_KW(8)
 #undef TTT_KW
@@ -1375,9 +1437,16 @@ hipError_t launch_keep_state(const T* W0, const T* Wcur, T* Ws, const uint8_t* d
 
 template <typename T>
 hipError_t launch_doc_grad_reset(float* G, T* Gsh, float* dW0, const uint8_t* docs, int B, int k, int c, int64_t df,
-                                 hipStream_t s) {
+                                 hipStream_t s, float* dWi) {
   if (B == 0 || df == 0) return hipSuccess;
-  k_doc_grad_reset<T><<<(unsigned)cdiv(df / 4, 256), 256, 0, s>>>(G, Gsh, dW0, docs, B, k, c, df);
+  k_doc_grad_reset<T><<<(unsigned)cdiv(df / 4, 256), 256, 0, s>>>(G, Gsh, dW0, docs, B, k, c, df, dWi);
+  return hipGetLastError();
+}
+
+hipError_t launch_resume_split(const float* Tt, const uint8_t* docs, float* dW0, float* dWi, int B, int k, int64_t df,
+                               bool have_dW0, hipStream_t s) {
+  if (B == 0 || df == 0) return hipSuccess;
+  k_resume_split<<<(unsigned)cdiv(df / 4, 256), 256, 0, s>>>(Tt, docs, dW0, dWi, B, k, df, have_dW0);
   return hipGetLastError();
 }
 
@@ -1468,7 +1537,7 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
                                               int, int, int, float, float, float, bool, hipStream_t, int64_t,     \
                                               const uint8_t*);                                                    \
   template hipError_t launch_doc_grad_reset<T>(float*, T*, float*, const uint8_t*, int, int, int, int64_t,       \
-                                               hipStream_t);                                                      \
+                                               hipStream_t, float*);                                              \
   template hipError_t launch_keep_state<T>(const T*, const T*, T*, const uint8_t*, bool, int, int, int, int64_t,  \
                                            hipStream_t);                                                          \
   template hipError_t launch_mse_update<T>(const T*, const T*, const T*, float*, T*, bool, int, int, int, int, int, \
@@ -1476,7 +1545,7 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
   template hipError_t launch_produce_z_bwd<T>(const T*, const T*, const T*, const T*, T*, int64_t, int, int, int,  \
                                               hipStream_t);                                                       \
   template hipError_t launch_conv_bwd<T>(const T*, const T*, const T*, T*, float*, int64_t, int, int, int,        \
-                                         hipStream_t, const uint8_t*, int, bool);                                 \
+                                         hipStream_t, const uint8_t*, int, bool, const T*, T*);                   \
   template hipError_t launch_zero<T>(T*, int64_t, hipStream_t);                                                   \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
                                           const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t,  \

@@ -96,10 +96,16 @@ hipError_t launch_mse_apply_gen(const T* Zt, const T* Vt, const T* W0, const T* 
                                 int n, int d, int f, int C, int c, float rscale, float vscale, float oscale, bool gen,
                                 hipStream_t s, int64_t wstride = 0, const uint8_t* umask = nullptr);
 // MSE backward, packed rows: where chunk c starts row b's document, dW0 += G[b] (rows in order) and G[b] (and
-// Gsh[b]) = 0.
+// Gsh[b]) = 0.  With dWi (resumed rows, c = 0): a row whose chunk 0 is not flagged continues from W_init, so
+// dWi[b] = G[b] and dW0 takes nothing of it; flagged rows get dWi[b] = 0.
 template <typename T>
 hipError_t launch_doc_grad_reset(float* G, T* Gsh, float* dW0, const uint8_t* docs, int B, int k, int c, int64_t df,
-                                 hipStream_t s);
+                                 hipStream_t s, float* dWi = nullptr);
+// Dot backward, resumed rows: Tt [B, d, f] the rows' first-document gradients; dWi[b] = Tt[b] where row b
+// continues from W_init (chunk 0 not flagged), else 0; dW0 -= their sum (have_dW0: dW0 holds every document's
+// sum), else dW0 = 0.
+hipError_t launch_resume_split(const float* Tt, const uint8_t* docs, float* dW0, float* dWi, int B, int k, int64_t df,
+                               bool have_dW0, hipStream_t s);
 // Ws [B, k, d, f]: slot c gets the state the MSE apply of chunk c reads (W_down0
 // where a document starts, else Wcur [B, d, f]).
 template <typename T>
@@ -115,10 +121,13 @@ template <typename T>
 hipError_t launch_produce_z_bwd(const T* H, const T* Wg, const T* Wu, const T* dZ, T* G, int64_t rows, int n, int d,
                                 int f, hipStream_t s);
 // Backward of the causal convolution (fwd: of the forward-looking in-chunk one): dX0 [rows, d] and the
-// tap-gradient partials part [conv_bwd_partials(rows), d, K] (fp32).
+// tap-gradient partials part [conv_bwd_partials(rows), d, K] (fp32); with halo [B, K-1, d] (resumed rows, causal
+// only) the first document of a row not flagged at chunk 0 reads it, and dhalo [B, K-1, d] (if not null) gets
+// its gradient (zero for flagged rows and with fwd).
 template <typename T>
 hipError_t launch_conv_bwd(const T* X0, const T* cw, const T* dY, T* dX0, float* part, int64_t rows, int n, int d,
-                           int K, hipStream_t s, const uint8_t* docs, int C, bool fwd = false);
+                           int K, hipStream_t s, const uint8_t* docs, int C, bool fwd = false,
+                           const T* halo = nullptr, T* dhalo = nullptr);
 // Number of tap-gradient partials launch_conv_bwd writes: a thread takes
 // kConvBwdGroups groups of kConvBwdRows rows of one channel chunk.
 constexpr int kConvBwdRows = 8, kConvBwdGroups = 32;

@@ -254,6 +254,26 @@ typedef struct {
    * in-chunk convolution (ttt_layer_options.conv_forward), 0 for the causal
    * one; other values TTT_ERR_ARG. */
   int conv_forward;
+  /* Resumed rows, as the forward call took them (ttt_layer_options.W_init and
+   * x0_halo): a row continues its sequence -- its first document starts from
+   * W_init[b] and its causal convolution reads x0_halo[b] before the first
+   * token -- unless doc_starts flags its chunk 0.  W_init [B, d, f] fp32
+   * (DEVICE, 16-byte aligned) or NULL; then dW_init [B, d, f] fp32 (DEVICE,
+   * 16-byte aligned) is required and receives each row's initial-state
+   * gradient (zero for rows flagged at chunk 0), and dW_down0 sums only the
+   * documents that start from W_down0.  With packed documents the dot
+   * objective takes a continuing row's first document off the sum of all of
+   * them, in fp32, so dW_down0 carries rounding of order 1e-7 of that
+   * document's gradient.  x0_halo [B, K-1, d] dtype (DEVICE, 16-byte aligned,
+   * whole layer only; the chunk loop's backward reads neither halo field) or
+   * NULL; then dx0_halo [B, K-1, d] dtype is required and receives the halo
+   * rows' gradient (zero for rows flagged at chunk 0, and everywhere with the
+   * forward-looking convolution, which never reads it).  A gradient pointer
+   * without its input, or a missing one: TTT_ERR_ARG. */
+  const float* W_init;
+  const void* x0_halo;
+  float* dW_init;
+  void* dx0_halo;
 } ttt_backward_options;
 
 /* ---- backward of the dot chunk loop ---- */
@@ -289,7 +309,7 @@ int ttt_core_backward_workspace_bytes(const ttt_inplace_shape* shape, int dtype,
  * document (the reversed scan restarts from zero where the forward order's
  * documents end), and dW_down0 receives every document's sum, formed by one
  * more contraction over all chunks (2 d f flop per token).  Update masks:
- * ttt_core_backward_ex; resumed rows are not handled.  Inputs as in
+ * ttt_core_backward_ex (which also takes resumed rows).  Inputs as in
  * ttt_core_apply_update; conv_k is not used.  seq_len == 0 or batch == 0
  * gives dW_down0 = 0 and touches nothing else.  Errors as for every entry
  * point (a too small workspace: TTT_ERR_WORKSPACE). */
@@ -324,7 +344,7 @@ int ttt_core_backward_mse_workspace_bytes(const ttt_inplace_shape* shape, int dt
  * [B, k] (DEVICE, as ttt_layer_options.doc_starts; NULL: one document per
  * row) packs documents: at a document's first chunk G goes to dW_down0 and
  * restarts from zero for the chunk before.  Update masks:
- * ttt_core_backward_ex; resumed rows are not handled.
+ * ttt_core_backward_ex (which also takes resumed rows).
  * seq_len == 0 or batch == 0 gives dW_down0 = 0.  Errors as for every entry
  * point. */
 int ttt_core_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta, const void* Z, const void* Vhat,
@@ -375,8 +395,9 @@ int ttt_layer_backward(const ttt_inplace_shape* shape, int dtype, float eta, con
 
 /* The chunk loop's backward for either objective with options:
  * mode TTT_MODE_DOT (or TTT_MODE_DOT_SCAN) as ttt_core_backward, TTT_MODE_MSE as
- * ttt_core_backward_mse; W_states and doc_starts as there, update_mask as in
- * ttt_backward_options (conv_forward is not read).  Workspace: the matching
+ * ttt_core_backward_mse; W_states and doc_starts as there, update_mask,
+ * W_init and dW_init as in ttt_backward_options (conv_forward, x0_halo and
+ * dx0_halo are not read).  Workspace: the matching
  * ttt_core_backward_workspace_bytes or ttt_core_backward_mse_workspace_bytes.
  * Other arguments, rules and errors as for those calls. */
 int ttt_core_backward_ex(const ttt_inplace_shape* shape, int dtype, int mode, float eta, const void* Z,
@@ -411,7 +432,8 @@ int ttt_layer_backward_mse(const ttt_inplace_shape* shape, int dtype, float eta,
 /* The whole layer's backward for either objective with options: mode
  * TTT_MODE_DOT (or TTT_MODE_DOT_SCAN) as ttt_layer_backward, TTT_MODE_MSE as
  * ttt_layer_backward_mse, and every field of ttt_backward_options (the update
- * mask and the convolution's direction as the forward call took them; the
+ * mask, the convolution's direction and the resumed rows' W_init and
+ * x0_halo as the forward call took them, with their gradients; the
  * forward-looking convolution's gradient stays inside each chunk, as its
  * window does).  Workspace: ttt_layer_backward_workspace_bytes or
  * ttt_layer_backward_mse_workspace_bytes.  Other arguments, rules and errors

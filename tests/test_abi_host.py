@@ -292,6 +292,36 @@ def test_layer_backward_validation():
     assert call(0.1, ins, outs, _fake(), 1 << 40, shape=odd) == cw.TTT_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_backward_resume_validation(mode):
+    """Resumed rows in ttt_backward_options: each gradient goes with its input (W_init with dW_init; in the whole
+    layer x0_halo with dx0_halo), both 16-byte aligned, checked before any device work."""
+    lib = cw.lib()
+    s = cw.InplaceShape(2, 1024, 256, 512, 256, 4)
+    m = cw.TTT_MODE_MSE if mode else cw.TTT_MODE_DOT
+    bad = ctypes.c_void_p(0x100004)
+
+    def opts(Wi=None, halo=None, dWi=None, dhalo=None):
+        return cw.BackwardOptions(None, None, None, 0, Wi, halo, dWi, dhalo)
+
+    def core(o):
+        return lib.ttt_core_backward_ex(ctypes.byref(s), cw.TTT_BF16, m, 0.1, *[_fake() for _ in range(4)],
+                                        ctypes.byref(o), _fake(), _fake(), _fake(), _fake(), 1 << 40, None)
+
+    def layer(o):
+        return lib.ttt_layer_backward_ex(ctypes.byref(s), cw.TTT_BF16, m, 0.1, *[_fake() for _ in range(8)],
+                                         ctypes.byref(o), *[_fake() for _ in range(7)], _fake(), 1 << 40, None)
+
+    for call in (core, layer):
+        assert call(opts(Wi=_fake())) == cw.TTT_ERR_ARG              # no dW_init
+        assert call(opts(dWi=_fake())) == cw.TTT_ERR_ARG             # a gradient without its input
+        assert call(opts(Wi=bad, dWi=_fake())) == cw.TTT_ERR_ARG
+        assert call(opts(Wi=_fake(), dWi=bad)) == cw.TTT_ERR_ARG
+    assert layer(opts(halo=_fake())) == cw.TTT_ERR_ARG
+    assert layer(opts(dhalo=_fake())) == cw.TTT_ERR_ARG
+    assert layer(opts(halo=_fake(), dhalo=bad)) == cw.TTT_ERR_ARG
+
+
 def test_mse_backward_validation():
     """ttt_core_backward_mse: workspace sizes with and without kept states, and validation before device work."""
     lib = cw.lib()

@@ -502,3 +502,92 @@ def test_layer_backward_forward_conv_and_mask(mode, dtype):
                              update_mask=mask, conv_forward=True)
     for name, got, want in zip(GRAD_NAMES, grads, ref):
         assert rel(f64(got), want) < TOL[dtype], name
+
+
+# ---------------------------------------------------------------- resumed rows
+
+@pytest.mark.parametrize("mode,dtype,C,k", [("dot", "f32", 96, 4), ("dot", "bf16", 128, 4), ("dot", "bf16", 72, 3),
+                                            ("mse", "f32", 96, 4), ("mse", "bf16", 128, 4)])
+@pytest.mark.parametrize("packed", [False, True])
+def test_core_backward_resumed_rows(mode, dtype, C, k, packed):
+    """The chunk loop's backward of resumed rows (ttt_core_backward_ex with W_init): dZ, dVhat, dW_down0 and
+    dW_init against the oracle, on the fused scan with segments, the delta + scan path (chunk 72) and the MSE
+    recursion.  Packed: row 0 continues into a second document at chunk 2, row 1 is flagged at chunk 0 (it starts
+    from W_down0 and its dW_init is exactly zero).  The states the resumed forward call keeps give the same
+    results."""
+    cfg = cfg_of(dtype, 2, k, C, eta=0.05 if mode == "dot" else 0.5, seed=35).with_(mode=mode)
+    x = ti.backward_inputs(cfg)
+    r = ti.resume_inputs(cfg, seed=36)
+    g = {name: t.cuda() for name, t in x.items()}
+    Wi = r["W_init"].cuda()
+    starts = np.zeros((2, k), dtype=np.uint8)
+    if packed:
+        starts[0, 2] = 1
+        starts[1, 0] = 1
+    ds = torch.from_numpy(starts).cuda() if packed else None
+    fn = cw.ttt_core_backward if mode == "dot" else cw.ttt_core_backward_mse
+    got = fn(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta, doc_starts=ds, W_init=Wi)
+    Ws = torch.empty(2, k, cfg.d_model, cfg.d_ff, dtype=g["Z"].dtype, device="cuda")
+    cw.ttt_core_apply_update(g["Z"], g["Vhat"], g["W_down0"], C, cfg.eta, mode, W_states=Ws, doc_starts=ds,
+                             W_init=Wi)
+    kept = fn(g["Z"], g["Vhat"], g["W_down0"], g["dO"], C, cfg.eta, doc_starts=ds, W_init=Wi, W_states=Ws)
+    torch.cuda.synchronize()
+    Z, V, W0, dO = (ti.to_f64(x[name]) for name in ("Z", "Vhat", "W_down0", "dO"))
+    Wi64 = r["W_init"].double().numpy()
+    outs = [orc.resumed_core_backward(Z[b], V[b], W0, Wi64[b], C, cfg.eta, dO[b], mode,
+                                      doc_starts=starts[b] if packed else None) for b in range(2)]
+    ref = (np.stack([o[0] for o in outs]), np.stack([o[1] for o in outs]), sum(o[2] for o in outs),
+           np.stack([o[3] for o in outs]))
+    for res in (got, kept):
+        for name, a, b in zip(("dZ", "dVhat", "dW_down0"), res, ref):
+            assert rel(f64(a), b) < TOL[dtype], name
+        for b in range(2):
+            if packed and b == 1:
+                assert not torch.any(res[3][1])
+            else:
+                assert rel(f64(res[3][b]), ref[3][b]) < TOL[dtype], ("dW_init", b)
+    if not packed:                       # every row continues: nothing starts from W_down0
+        assert not torch.any(got[2])
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", ["both", "halo_only", "forward_conv"])
+def test_layer_backward_resumed_rows(mode, dtype, case):
+    """The whole layer's backward of resumed rows (ttt_layer_backward_ex with W_init and x0_halo, K = 4, ragged
+    264 x 392, four chunks): three rows -- one continuing into a second document at chunk 2, one flagged at chunk 0
+    (zero dW_init and dx0_halo), one continuing to its end -- every gradient against the oracle, dW_init and
+    dx0_halo included.  halo_only: the first documents start from W_down0; forward_conv: the halo is never read
+    (dx0_halo zero)."""
+    C, K = 128, 4
+    cfg = ti.InplaceConfig("lbwdr", 3, 4 * C, 264, 392, C, 0.05 if mode == "dot" else 0.5, mode, dtype, conv_k=K,
+                           seed=67)
+    x = ti.inplace_inputs(cfg)
+    dO = ti.backward_inputs(cfg.with_(seed=68))["dO"]
+    r = ti.resume_inputs(cfg, seed=69)
+    starts = np.array([[0, 0, 1, 0], [1, 0, 0, 1], [0, 0, 0, 0]], dtype=np.uint8)
+    g = {name: t.cuda() for name, t in x.items()}
+    Wi = None if case == "halo_only" else r["W_init"].cuda()
+    fwd = case == "forward_conv"
+    res = cw.ttt_layer_backward(*layer_args(g), dO.cuda(), C, cfg.eta, mode=mode,
+                                doc_starts=torch.from_numpy(starts).cuda(), conv_forward=fwd, W_init=Wi,
+                                x0_halo=r["x0_halo"].cuda())
+    torch.cuda.synchronize()
+    assert len(res) == 9 and (res[7] is None) == (Wi is None)
+    ref = orc.layer_backward(*(ti.to_f64(x[name]) for name in ("H", "X0", "W_gate", "W_up", "W_down0", "W_target",
+                                                               "conv_w")), C, cfg.eta, ti.to_f64(dO),
+                             doc_starts=starts, mode=mode, conv_forward=fwd,
+                             W_init=None if Wi is None else r["W_init"].double().numpy(),
+                             x0_halo=ti.to_f64(r["x0_halo"]))
+    for name, got, want in zip(GRAD_NAMES, res[:7], ref[:7]):
+        assert rel(f64(got), want) < TOL[dtype], name
+    if Wi is not None:
+        for b in (0, 2):
+            assert rel(f64(res[7][b]), ref[7][b]) < TOL[dtype], ("dW_init", b)
+        assert not torch.any(res[7][1])
+    if fwd:
+        assert not torch.any(res[8])
+    else:
+        for b in (0, 2):
+            assert rel(f64(res[8][b]), ref[8][b]) < TOL[dtype], ("dx0_halo", b)
+        assert not torch.any(res[8][1])

@@ -284,6 +284,18 @@ def backward_inputs(cfg: InplaceConfig, seed: int | None = None) -> dict:
     return out
 
 
+def resume_inputs(cfg: InplaceConfig, seed: int) -> dict:
+    """Draw what a resumed row brings from an earlier call, on the CPU:
+    W_init [B, d, f] fp32 (a state: W_down0's distribution, per row) and
+    x0_halo [B, K-1, d] in the workload's dtype (X0's distribution)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    B, d, f, K = cfg.batch, cfg.d_model, cfg.d_ff, cfg.conv_k
+    var_w = cfg.var_down if cfg.var_down is not None else 1.0 / f
+    return {"W_init": _draw(gen, (B, d, f), var_w, torch.float32),
+            "x0_halo": _draw(gen, (B, K - 1, d), cfg.var_x0, _torch_dtype(cfg.dtype))}
+
+
 def lact_inputs(cfg: LactConfig, seed: int | None = None) -> dict:
     """Draw the LaCT layer inputs on the CPU.
 
