@@ -227,27 +227,34 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __rest
   // staged by token rows.
   const Staged<T, G::BP> st{smem};
   T* base = part ? R + (int64_t)bh * C * dh : O + ((int64_t)bh * n + (int64_t)sr.qc * C) * dh;
+  if (part) {
+    // R in the accumulators before any staging, so that the loads of V and of
+    // the rates are not held up behind LDS traffic; a lane outside the matrix
+    // reads the nearest valid element of V (never stored)
+#pragma unroll
+    for (int jq = 0; jq < G::NQB; ++jq) {
+      const int r = min(r0 + G::acc_q(jq), nrows - 1);
+      const int64_t tok = (int64_t)bh * n + (int64_t)sr.kc * C + r;
+      const float rate = eta_tok != nullptr ? eta_tok[tok] : 1.0f;
+#pragma unroll
+      for (int ib = 0; ib < G::NPB; ++ib) {
+        const int i = min(i0 + G::acc_p(ib, 0), dh - 4);
+        const f32x4 vv = load4(v + tok * dh + i);
+        f32x4& y = acc[ib][jq];
+        y = loss_dot ? -vv : y - vv;
+        y *= rate;
+      }
+    }
+  }
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
     for (int jq = 0; jq < G::NQB; ++jq) {
       const int q = G::acc_q(jq) - ps * RPP;
       if (q < 0 || q >= RPP) continue;
-      // a lane outside the matrix reads the nearest valid element of V (never stored)
-      const int r = min(r0 + G::acc_q(jq), nrows - 1);
-      const int64_t tok = (int64_t)bh * n + (int64_t)sr.kc * C + r;
-      const float rate = (part && eta_tok != nullptr) ? eta_tok[tok] : 1.0f;
 #pragma unroll
-      for (int ib = 0; ib < G::NPB; ++ib) {
-        f32x4 y = acc[ib][jq];
-        if (part) {
-          const int i = min(i0 + G::acc_p(ib, 0), dh - 4);
-          const f32x4 vv = load4(v + tok * dh + i);
-          y = loss_dot ? -vv : y - vv;
-          y *= rate;
-        }
-        st.put4(q, G::acc_p(ib, 0), y[0], y[1], y[2], y[3]);
-      }
+      for (int ib = 0; ib < G::NPB; ++ib)
+        st.put4(q, G::acc_p(ib, 0), acc[ib][jq][0], acc[ib][jq][1], acc[ib][jq][2], acc[ib][jq][3]);
     }
     __syncthreads();
     const int rows = max(0, min(RPP, tn - ps * RPP));
