@@ -230,12 +230,16 @@ def _update_backward(kc, vc, W1, W3, W2, gG1, gG3, gG2):
     return dk, dv, dA_f.T @ kc, dU_f.T @ kc, dW2
 
 
-def lact_backward(q, k, v, W1, W3, W2, chunk, eta, dO, order="update_then_apply"):
+def lact_backward(q, k, v, W1, W3, W2, chunk, eta, dO, order="update_then_apply", update_mask=None):
     """Gradients of a loss that depends on the output O of lact_layer (the
-    squared error, plain GD, no mask or other variant) with respect to every
-    input, given dO = dLoss/dO [B, H, n, dh]: returns (dq, dk, dv
-    [B, H, n, dh], dW1, dW3 [H, m, dh], dW2 [H, dh, m]); the initial weights
-    are shared by the batch rows, so their gradients add over rows.
+    squared error, plain GD, optionally an update mask; no other variant) with
+    respect to every input, given dO = dLoss/dO [B, H, n, dh]: returns (dq,
+    dk, dv [B, H, n, dh], dW1, dW3 [H, m, dh], dW2 [H, dh, m]); the initial
+    weights are shared by the batch rows, so their gradients add over rows.
+
+    `update_mask` [n_chunks] as in lact_layer: a chunk whose flag is zero is
+    applied but takes no step, so the state passes it unchanged and its keys
+    and values reach nothing (their gradients are zero).
 
     The chain rule through the chunk loop (LaCT Model Architecture §1, eq.
     (3)-(4)), from the last chunk back.  With W_c the state chunk c's update
@@ -258,10 +262,11 @@ def lact_backward(q, k, v, W1, W3, W2, chunk, eta, dO, order="update_then_apply"
         for h in range(Hn):
             states = []                          # the state each chunk's update starts from
             w = (W1[h].copy(), W3[h].copy(), W2[h].copy())
-            for s, e in bounds:
+            for c, (s, e) in enumerate(bounds):
                 states.append(w)
-                g1, g3, g2 = swiglu_grads(k[b, h, s:e], v[b, h, s:e], *w)
-                w = (w[0] - eta * g1, w[1] - eta * g3, w[2] - eta * g2)
+                if update_mask is None or update_mask[c]:
+                    g1, g3, g2 = swiglu_grads(k[b, h, s:e], v[b, h, s:e], *w)
+                    w = (w[0] - eta * g1, w[1] - eta * g3, w[2] - eta * g2)
             states.append(w)
             g = [np.zeros_like(W1[h]), np.zeros_like(W3[h]), np.zeros_like(W2[h])]   # gradient after the last chunk
             for c in range(len(bounds) - 1, -1, -1):
@@ -269,9 +274,12 @@ def lact_backward(q, k, v, W1, W3, W2, chunk, eta, dO, order="update_then_apply"
                 if order == "update_then_apply":       # the queries see the updated state
                     dqc, a1, a3, a2 = _apply_backward(q[b, h, s:e], *states[c + 1], dO[b, h, s:e])
                     g = [g[0] + a1, g[1] + a3, g[2] + a2]
-                dkc, dvc, u1, u3, u2 = _update_backward(k[b, h, s:e], v[b, h, s:e], *states[c],
-                                                        -eta * g[0], -eta * g[1], -eta * g[2])
-                g = [g[0] + u1, g[1] + u3, g[2] + u2]
+                if update_mask is None or update_mask[c]:
+                    dkc, dvc, u1, u3, u2 = _update_backward(k[b, h, s:e], v[b, h, s:e], *states[c],
+                                                            -eta * g[0], -eta * g[1], -eta * g[2])
+                    g = [g[0] + u1, g[1] + u3, g[2] + u2]
+                else:                                  # no step: the state passes through
+                    dkc, dvc = np.zeros((e - s, dh)), np.zeros((e - s, dh))
                 if order == "apply_then_update":       # the queries see the state before the update
                     dqc, a1, a3, a2 = _apply_backward(q[b, h, s:e], *states[c], dO[b, h, s:e])
                     g = [g[0] + a1, g[1] + a3, g[2] + a2]

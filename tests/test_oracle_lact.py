@@ -292,7 +292,7 @@ def test_muon_update_in_the_layer():
 
 # ---------------------------------------------------------------- backward of the layer
 
-def _torch_lact_layer(q, k, v, W1, W3, W2, chunk, eta, order):
+def _torch_lact_layer(q, k, v, W1, W3, W2, chunk, eta, order, update_mask=None):
     """The LaCT layer in torch float64 with the inner gradient taken by autograd itself (create_graph, so that an
     outer backward differentiates through it), for the backward's pin."""
     B, Hn, n, dh = q.shape
@@ -302,13 +302,14 @@ def _torch_lact_layer(q, k, v, W1, W3, W2, chunk, eta, order):
         for h in range(Hn):
             w = [W1[h], W3[h], W2[h]]
             outs = []
-            for s in range(0, n, chunk):
+            for c, s in enumerate(range(0, n, chunk)):
                 qc, kc, vc = q[b, h, s:s + chunk], k[b, h, s:s + chunk], v[b, h, s:s + chunk]
                 if order == "apply_then_update":
                     outs.append(_torch_swiglu(qc, *w))
-                loss = 0.5 * ((_torch_swiglu(kc, *w) - vc) ** 2).sum()
-                grads = torch.autograd.grad(loss, w, create_graph=True)
-                w = [wi - eta * gi for wi, gi in zip(w, grads)]
+                if update_mask is None or update_mask[c]:
+                    loss = 0.5 * ((_torch_swiglu(kc, *w) - vc) ** 2).sum()
+                    grads = torch.autograd.grad(loss, w, create_graph=True)
+                    w = [wi - eta * gi for wi, gi in zip(w, grads)]
                 if order == "update_then_apply":
                     outs.append(_torch_swiglu(qc, *w))
             heads.append(torch.cat(outs))
@@ -336,6 +337,31 @@ def test_lact_backward_matches_autograd(order, n, chunk):
     # the forward it differentiates is the oracle's layer
     O, *_ = orc.lact_layer(q, k, v, W1, W3, W2, chunk, eta, order)
     np.testing.assert_allclose(O, out.detach().numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
+def test_lact_backward_with_update_mask_matches_autograd(order):
+    """A masked chunk is applied but takes no step: autograd of the layer that skips those steps gives every
+    gradient, the masked chunks' dk and dv are exactly zero, and the forward differentiated is the oracle's masked
+    layer; an all-ones mask is the unmasked backward."""
+    q, k, v, W1, W3, W2 = _problem(74, B=2, H=2, n=16, dh=3, m=5)
+    eta, chunk = 0.7, 4
+    mask = [1, 0, 0, 1]
+    dO = np.random.default_rng(75).standard_normal(q.shape)
+    ours = orc.lact_backward(q, k, v, W1, W3, W2, chunk, eta, dO, order, update_mask=mask)
+    ts = [torch.tensor(a, requires_grad=True) for a in (q, k, v, W1, W3, W2)]
+    out = _torch_lact_layer(*ts, chunk, eta, order, update_mask=mask)
+    (out * torch.from_numpy(dO)).sum().backward()
+    for got, t in zip(ours, ts):
+        want = np.zeros(t.shape) if t.grad is None else t.grad.numpy()
+        np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+    for g in ours[1:3]:
+        assert not g[:, :, 4:12].any()
+    O, *_ = orc.lact_layer(q, k, v, W1, W3, W2, chunk, eta, order, update_mask=mask)
+    np.testing.assert_allclose(O, out.detach().numpy(), rtol=1e-12, atol=1e-12)
+    plain = orc.lact_backward(q, k, v, W1, W3, W2, chunk, eta, dO, order)
+    for a, b in zip(orc.lact_backward(q, k, v, W1, W3, W2, chunk, eta, dO, order, update_mask=[1] * 4), plain):
+        np.testing.assert_array_equal(a, b)
 
 
 def test_lact_backward_finite_differences_and_eta_zero():
