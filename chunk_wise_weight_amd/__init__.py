@@ -10,7 +10,7 @@ Functions keep the C names:
   ttt_chunk_apply_update, ttt_chunk_apply_update_noalloc, ttt_core_apply_update(_ex), ttt_core_backward,
   ttt_core_backward_mse, ttt_layer_backward, ttt_layer_backward_mse, ttt_produce_z,
   ttt_produce_vhat, ttt_chunk_delta, ttt_chunk_scan, ttt_chunk_update_scan,
-  ttt_chunk_apply, ttt_lact_swiglu, ttt_lact_swiglu_backward, plus the workspace queries.
+  ttt_chunk_apply, ttt_lact_swiglu, ttt_lact_swiglu_backward (and its _ex form), plus the workspace queries.
 """
 from ._lib import (  # noqa: F401
     TTT_OK, TTT_ERR_ARG, TTT_ERR_SHAPE, TTT_ERR_DTYPE, TTT_ERR_WORKSPACE, TTT_ERR_DEVICE,

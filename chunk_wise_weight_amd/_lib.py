@@ -120,6 +120,8 @@ _SIGNATURES = {
                                 ctypes.POINTER(LactOptions), _P, _P, _P, _P, _P, _S, _P]),
     "ttt_lact_backward_workspace_bytes": (_I, [ctypes.POINTER(LactShape), _I, ctypes.POINTER(_S)]),
     "ttt_lact_swiglu_backward": (_I, [ctypes.POINTER(LactShape), _I, _I, _F] + [_P] * 13 + [_P, _S, _P]),
+    "ttt_lact_swiglu_backward_ex": (_I, [ctypes.POINTER(LactShape), _I, _F] + [_P] * 7 +
+                                    [ctypes.POINTER(LactOptions)] + [_P] * 6 + [_P, _S, _P]),
 }
 
 _lib = None
@@ -626,6 +628,16 @@ def ttt_lact_workspace_bytes(shape: LactShape, dtype: torch.dtype) -> int:
     return out.value
 
 
+def _host_flags(update_mask, n, chunk):
+    """A per-chunk host flag sequence as a ctypes uint8 array (kept alive by the caller), or None."""
+    if update_mask is None:
+        return None
+    flags = [1 if bool(x) else 0 for x in (update_mask.tolist() if hasattr(update_mask, "tolist") else update_mask)]
+    if chunk <= 0 or len(flags) != n // chunk:
+        raise ValueError(f"update_mask needs {n // chunk if chunk > 0 else 0} entries, got {len(flags)}")
+    return (ctypes.c_ubyte * max(1, len(flags)))(*flags)
+
+
 def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_then_apply", O=None, finals=None,
                     workspace=None, update_mask=None, eta_tok=None, loss="mse", weight_norm=False, muon=False,
                     side=None):
@@ -663,13 +675,7 @@ def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_t
                                      _ptr(W1), _ptr(W3), _ptr(W2), _ptr(O), _ptr(W1f), _ptr(W3f), _ptr(W2f),
                                      _ptr(ws), nbytes, _stream(dev)), "ttt_lact_swiglu")
         return O, W1f, W3f, W2f
-    mask = None
-    if update_mask is not None:
-        flags = [1 if bool(x) else 0 for x in
-                 (update_mask.tolist() if hasattr(update_mask, "tolist") else update_mask)]
-        if chunk <= 0 or len(flags) != n // chunk:
-            raise ValueError(f"update_mask needs {n // chunk if chunk > 0 else 0} entries, got {len(flags)}")
-        mask = (ctypes.c_ubyte * max(1, len(flags)))(*flags)
+    mask = _host_flags(update_mask, n, chunk)
     if eta_tok is not None:
         _need(eta_tok, "eta_tok", (B, Hh, n), torch.float32, dev)
     if loss not in ("mse", "dot"):
@@ -693,9 +699,11 @@ def ttt_lact_backward_workspace_bytes(shape: LactShape, dtype: torch.dtype) -> i
 
 
 def ttt_lact_swiglu_backward(q, k, v, W1, W3, W2, dO, chunk: int, eta: float, order="update_then_apply",
-                             grads=None, workspace=None):
-    """Backward of the LaCT layer (squared error, plain GD) given dO = dLoss/dO [B, H, n, dh].  Returns (dq, dk,
-    dv [B, H, n, dh] in the inputs' dtype, dW1, dW3 [H, m, dh], dW2 [H, dh, m] fp32, summed over the batch rows)."""
+                             grads=None, workspace=None, update_mask=None):
+    """Backward of the LaCT layer (squared error, plain GD) given dO = dLoss/dO [B, H, n, dh]; update_mask, a host
+    sequence of n // chunk flags as the forward layer took it (through ttt_lact_swiglu_backward_ex).  Returns (dq,
+    dk, dv [B, H, n, dh] in the inputs' dtype, dW1, dW3 [H, m, dh], dW2 [H, dh, m] fp32, summed over the batch
+    rows)."""
     B, Hh, n, dh = q.shape
     m = W1.shape[1]
     dt, dev = q.dtype, q.device
@@ -713,6 +721,14 @@ def ttt_lact_swiglu_backward(q, k, v, W1, W3, W2, dO, chunk: int, eta: float, or
     nbytes = ttt_lact_backward_workspace_bytes(shape, dt)
     ws = _workspace(nbytes, dev, workspace)
     ordc = _ORDERS[order] if isinstance(order, str) else int(order)
+    if update_mask is not None:
+        mask = _host_flags(update_mask, n, chunk)
+        opts = LactOptions(ordc, ctypes.cast(mask, ctypes.c_void_p), None, 0, 0, 0, None, None, None)
+        _check(lib().ttt_lact_swiglu_backward_ex(ctypes.byref(shape), _dt(dt), float(eta), _ptr(q), _ptr(k),
+                                                 _ptr(v), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(dO), ctypes.byref(opts),
+                                                 *[_ptr(g) for g in grads], _ptr(ws), nbytes, _stream(dev)),
+               "ttt_lact_swiglu_backward_ex")
+        return grads
     _check(lib().ttt_lact_swiglu_backward(ctypes.byref(shape), _dt(dt), ordc, float(eta), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(W1), _ptr(W3), _ptr(W2), _ptr(dO), *[_ptr(g) for g in grads],
                                           _ptr(ws), nbytes, _stream(dev)), "ttt_lact_swiglu_backward")

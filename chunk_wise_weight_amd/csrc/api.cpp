@@ -1259,6 +1259,24 @@ int ttt_lact_swiglu_backward(const ttt_lact_shape* shape, int dtype, int order, 
                              const void* k, const void* v, const void* W1, const void* W3, const void* W2,
                              const void* dO, void* dq, void* dk, void* dv, float* dW1, float* dW3, float* dW2,
                              void* workspace, size_t workspace_bytes, void* stream) {
+  ttt_lact_options opt{};
+  opt.order = order;
+  return ttt_lact_swiglu_backward_ex(shape, dtype, eta, q, k, v, W1, W3, W2, dO, &opt, dq, dk, dv, dW1, dW3, dW2,
+                                     workspace, workspace_bytes, stream);
+}
+
+int ttt_lact_swiglu_backward_ex(const ttt_lact_shape* shape, int dtype, float eta, const void* q, const void* k,
+                                const void* v, const void* W1, const void* W3, const void* W2, const void* dO,
+                                const ttt_lact_options* options, void* dq, void* dk, void* dv, float* dW1,
+                                float* dW3, float* dW2, void* workspace, size_t workspace_bytes, void* stream) {
+  if (options == nullptr) return TTT_ERR_ARG;
+  const int order = options->order;
+  if ((options->loss != 0 && options->loss != 1) || (options->weight_norm != 0 && options->weight_norm != 1) ||
+      (options->muon != 0 && options->muon != 1))
+    return TTT_ERR_ARG;
+  // the variants of the update itself have no backward here
+  if (options->eta_tok != nullptr || options->loss != 0 || options->weight_norm != 0 || options->muon != 0)
+    return TTT_ERR_UNSUPPORTED;
   int st = check_lact(shape, dtype);
   if (st != TTT_OK) return st;
   if (order != TTT_UPDATE_THEN_APPLY && order != TTT_APPLY_THEN_UPDATE) return TTT_ERR_ARG;
@@ -1283,7 +1301,7 @@ int ttt_lact_swiglu_backward(const ttt_lact_shape* shape, int dtype, int order, 
     return r;
   }
   ttt::LactBwdArgs a{B, H, n, dh, m, C, order, eta, q, k, v, W1, W3, W2, dO, dq, dk, dv, dW1, dW3, dW2,
-                     (char*)workspace};
+                     (char*)workspace, options->update_mask};
   return dev(dtype == TTT_BF16 ? ttt::launch_lact_backward<bf16>(a, s) : ttt::launch_lact_backward<float>(a, s));
 }
 

@@ -737,7 +737,12 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
     }
     if (sr.nk > 0 && a.update_mask != nullptr && a.update_mask[sr.kc] == 0) sr.nk = 0;   // applied only
     if (a.keys_only) sr.nq = 0;                                   // the backward's recompute: states only
-    if (sr.nq == 0 && sr.nk == 0) continue;
+    // a chunk that does not update passes the state on unchanged: its kept slot is the same state
+    const bool passes = sr.nk == 0 && sr.kc < k;
+    if (sr.nq == 0 && sr.nk == 0) {
+      if (passes && (e = keep_slot(sr.kc + 1)) != hipSuccess) return e;
+      continue;
+    }
     const int tq1 = (int)(cdiv(sr.nq, Wide::BQ) + cdiv(sr.nk, Wide::BQ));
     if (want()) k_lact_fwd1<T><<<(unsigned)(cdiv(m, Wide::BP / 2) * tq1 * BH), Wide::NT, 0, s>>>(q, kk, W1s, W3s, Hh, A, U, BH, n,
                                                                                    dh, m, C, sr);
@@ -747,7 +752,10 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
       k_lact_fwd2<T><<<(unsigned)(cdiv(dh, Wide::BP) * tq2 * BH), Wide::NT, 0, s>>>(Hh, W2s, v, O, R, BH, n, dh, m, C,
                                                                                  sr, eta_tok, a.loss_dot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (sr.nk == 0) continue;
+    if (sr.nk == 0) {
+      if (passes && (e = keep_slot(sr.kc + 1)) != hipSuccess) return e;
+      continue;
+    }
     if (want()) k_lact_dh<T><<<(unsigned)(cdiv(m, Wide::BP) * cdiv(sr.nk, Wide::BQ) * BH), Wide::NT, 0, s>>>(
         R, W2s, A, U, dA, dU, BH, dh, m, C, sr.nk);
     if ((e = hipGetLastError()) != hipSuccess) return e;

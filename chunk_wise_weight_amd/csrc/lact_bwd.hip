@@ -260,6 +260,15 @@ __global__ __launch_bounds__(256) void k_lact_neg(const T* __restrict__ src, T* 
   store4(dst + (int64_t)blockIdx.y * dstride + e, -x[0], -x[1], -x[2], -x[3]);
 }
 
+// dst[bh][t][j] = 0 for one chunk's rows of a [BH, n, dh] buffer (dst already
+// offset to the chunk; n elements per row group, row group stride dstride).
+template <typename T>
+__global__ __launch_bounds__(256) void k_lact_zero_rows(T* __restrict__ dst, int64_t n, int64_t dstride) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  store4(dst + (int64_t)blockIdx.y * dstride + e, 0.f, 0.f, 0.f, 0.f);
+}
+
 // R = Y - v for one chunk, formed in fp32 and rounded once: Y [BH, C, dh] fp32,
 // v rows of [BH, n, dh] at the chunk's offset (row group stride vstride), R
 // [BH, C, dh]; four elements per thread.
@@ -419,6 +428,7 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     f.ws = a.ws + L.fwd;
     f.keys_only = 1;
     f.keep = a.ws + L.keep;
+    f.update_mask = a.update_mask;
     if ((e = launch_lact<T>(f, s)) != hipSuccess) return e;
     if ((e = launch_zero<float>(g, (int64_t)BH * 3 * md, s)) != hipSuccess) return e;
   }
@@ -579,7 +589,16 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     const T* Wc = keep + (int64_t)c * slot;
     const T* Wn = keep + (int64_t)(c + 1) * slot;
     if (a.order == 0 && (e = query_backward(Wn, c)) != hipSuccess) return e;
-    if ((e = update_backward(Wc, c)) != hipSuccess) return e;
+    if (a.update_mask == nullptr || a.update_mask[c] != 0) {
+      if ((e = update_backward(Wc, c)) != hipSuccess) return e;
+    } else {
+      // no step: the state gradient passes through, and the chunk's keys and values reach nothing
+      const dim3 gz((unsigned)cdiv64(Scd / 4, 256), (unsigned)BH);
+      k_lact_zero_rows<T><<<gz, 256, 0, s>>>((T*)a.dk + (int64_t)c * C * dh, Scd, Sn);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      k_lact_zero_rows<T><<<gz, 256, 0, s>>>((T*)a.dv + (int64_t)c * C * dh, Scd, Sn);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (a.order != 0 && (e = query_backward(Wc, c)) != hipSuccess) return e;
   }
   k_lact_gsum<<<dim3((unsigned)cdiv64(md / 4, 256), (unsigned)(3 * H)), 256, 0, s>>>(g, a.dW1, a.dW3, a.dW2, B, H, md);

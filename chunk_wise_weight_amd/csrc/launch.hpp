@@ -175,6 +175,7 @@ struct LactBwdArgs {
   void *dq, *dk, *dv;
   float *dW1, *dW3, *dW2;
   char* ws;
+  const unsigned char* update_mask;   // HOST [n / C] as in LactArgs, or null
 };
 template <typename T>
 hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s);

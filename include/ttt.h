@@ -606,8 +606,9 @@ int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta,
 int ttt_lact_backward_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* bytes);
 
 /* Gradients of a loss that depends on the output O of ttt_lact_swiglu (the
- * squared error, plain GD; no mask, per-token rates, dot loss, normalisation or
- * Muon) with respect to every input, given dO = dLoss/dO [B, H, n, dh] (dtype)
+ * squared error, plain GD; an update mask through ttt_lact_swiglu_backward_ex,
+ * no per-token rates, dot loss, normalisation or Muon) with respect to every
+ * input, given dO = dLoss/dO [B, H, n, dh] (dtype)
  * (review of "Test-Time Training Done Right", LaCT Model Architecture §1,
  * eq. (3)-(4), by the chain rule through the chunk loop):
  *   dq, dk, dv   [B, H, n, dh] dtype
@@ -628,6 +629,22 @@ int ttt_lact_swiglu_backward(const ttt_lact_shape* shape, int dtype, int order, 
                              const void* W1, const void* W3, const void* W2, const void* dO,
                              void* dq, void* dk, void* dv, float* dW1, float* dW3, float* dW2,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ttt_lact_swiglu_backward with the forward call's ttt_lact_options (NULL:
+ * TTT_ERR_ARG): `order` and `update_mask` (HOST, [n / chunk], as for
+ * ttt_lact_swiglu_ex) are taken -- a chunk whose flag is zero was applied but
+ * took no step, so the state gradient passes it unchanged and its dk and dv
+ * rows are zero.  The update's variants have no backward here: eta_tok, the
+ * dot loss, weight_norm or muon give TTT_ERR_UNSUPPORTED (invalid values of
+ * the flags TTT_ERR_ARG).  side_stream and its events are not read (the
+ * backward runs as one chain on `stream`).  Other arguments, workspace and
+ * errors as for ttt_lact_swiglu_backward. */
+int ttt_lact_swiglu_backward_ex(const ttt_lact_shape* shape, int dtype, float eta,
+                                const void* q, const void* k, const void* v,
+                                const void* W1, const void* W3, const void* W2, const void* dO,
+                                const ttt_lact_options* options,
+                                void* dq, void* dk, void* dv, float* dW1, float* dW3, float* dW2,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -409,6 +409,17 @@ def test_lact_backward_validation():
     assert call(0, 1.0, [None] + args[1:], _fake(), nb.value) == cw.TTT_ERR_ARG   # null q
     assert call(0, 1.0, args, _fake(), nb.value - 1) == cw.TTT_ERR_WORKSPACE
     assert call(0, 1.0, args, None, nb.value) == cw.TTT_ERR_WORKSPACE
+    # the options form: NULL options, invalid flags, and the update variants that have no backward
+    ex = lambda o: lib.ttt_lact_swiglu_backward_ex(ctypes.byref(good), cw.TTT_BF16, 1.0, *args[:7],
+                                                   None if o is None else ctypes.byref(o), *args[7:], _fake(),
+                                                   nb.value, None)
+    assert ex(None) == cw.TTT_ERR_ARG
+    assert ex(cw.LactOptions(0, None, None, 2, 0, 0, None, None, None)) == cw.TTT_ERR_ARG
+    assert ex(cw.LactOptions(0, None, None, 1, 0, 0, None, None, None)) == cw.TTT_ERR_UNSUPPORTED   # dot loss
+    assert ex(cw.LactOptions(0, None, _fake(), 0, 0, 0, None, None, None)) == cw.TTT_ERR_UNSUPPORTED
+    assert ex(cw.LactOptions(0, None, None, 0, 1, 0, None, None, None)) == cw.TTT_ERR_UNSUPPORTED
+    assert ex(cw.LactOptions(0, None, None, 0, 0, 1, None, None, None)) == cw.TTT_ERR_UNSUPPORTED
+    assert ex(cw.LactOptions(7, None, None, 0, 0, 0, None, None, None)) == cw.TTT_ERR_ARG           # order
 
 
 def test_binding_refuses_cpu_tensors():

@@ -96,3 +96,30 @@ def test_lact_backward_workload_shape():
     errs = {name: rel(f64(got), want) for name, got, want in zip(NAMES, grads, oracle(cfg, x, dO))}
     print("  rel err " + "  ".join(f"{k} {v:.3e}" for k, v in errs.items()), flush=True)
     assert all(e < TOL["bf16"] for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("order", ["update_then_apply", "apply_then_update"])
+def test_lact_backward_with_update_mask(dtype, order):
+    """The backward with an update mask (ttt_lact_swiglu_backward_ex): chunks 1 and 2 of four are applied without
+    taking a step, so the recompute keeps their unchanged state and the reverse pass lets the state gradient through
+    them; their dk and dv rows are exactly zero, and every gradient matches the oracle's masked backward."""
+    cfg, x, dO = case(dtype, order, n=512, seed=83)
+    mask = [1, 0, 0, 1]
+    g = {k: v.cuda() for k, v in x.items()}
+    print(f"lact backward mask case: {dtype} {order} mask={mask}", flush=True)
+    grads = cw.ttt_lact_swiglu_backward(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], dO.cuda(), cfg.chunk,
+                                        cfg.eta, order, update_mask=mask)
+    torch.cuda.synchronize()
+    ref = olact.lact_backward(*(ti.to_f64(x[k]) for k in ("q", "k", "v", "W1", "W3", "W2")), cfg.chunk, cfg.eta,
+                              ti.to_f64(dO), order, update_mask=mask)
+    errs = {name: rel(f64(got), want) for name, got, want in zip(NAMES, grads, ref)}
+    assert all(e < TOL[dtype] for e in errs.values()), errs
+    for gt in grads[1:3]:
+        assert not torch.any(gt[:, :, cfg.chunk:3 * cfg.chunk])
+    # an all-ones mask is the plain backward, bit for bit
+    ones = cw.ttt_lact_swiglu_backward(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], dO.cuda(), cfg.chunk,
+                                       cfg.eta, order, update_mask=[1] * 4)
+    plain = run(cfg, x, dO)
+    for a, b in zip(ones, plain):
+        assert torch.equal(a, b)
