@@ -289,22 +289,6 @@ struct DmaOpMN {
   }
 };
 
-// Two operands of the same layout read one after the other along K: steps
-// 0 .. n1 - 1 from a, the rest from b (a contraction over K = K_a + K_b).
-template <class OP>
-struct Concat {
-  OP a, b;
-  int n1;
-  static constexpr int kReads = OP::kReads;
-  __device__ static __forceinline__ u32x4 frag(const char* t, int m0, int g) { return OP::frag(t, m0, g); }
-  __device__ __forceinline__ void issue(int ks, char* tile) const {
-    if (ks < n1)
-      a.issue(ks, tile);
-    else
-      b.issue(ks - n1, tile);
-  }
-};
-
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------- MFMA step

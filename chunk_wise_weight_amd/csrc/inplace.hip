@@ -891,16 +891,15 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
 
 // ------------------------------------------------------------------ backward of the dot chunk loop
 
-// Two operands of one tile shape read back to back along K: steps 0 .. n1 - 1
-// from the first, the rest from the second.  They share the LDS layout, so one
-// accumulator takes the sum of both contractions in one stream of K steps.
 // dZ_j = dO_j W_j + eta V^_j S_j for every chunk j, with W_j the state chunk j
 // was applied with and S_j = sum_{c>j} dO_c^T Z_c (Method §3's prefix form
 // differentiated; see the backward entry point).  P = d_ff columns of the
 // [d, f] states (MN-major: f contiguous), Q = the chunk's tokens (rows of
-// eta V^ and dO, [n, d]), K = d_model twice: one stream of K steps over
-// (S_j, eta V^_j), then (W_j, dO_j).  State j sits at W + b wsb + j wsc (S
-// likewise; its stride may be negative).  dZ [B, n, f] through LDS like O.
+// eta V^ and dO, [n, d]), K = d_model twice: one accumulator takes both
+// contractions, a K loop over (S_j, eta V^_j) and then one over (W_j, dO_j),
+// each with its own operand state (both live at once spill).  State j sits at
+// W + b wsb + j wsc (S likewise; its stride may be negative).  dZ [B, n, f]
+// through LDS like O.
 // The rows of V and dO are ldq elements apart (d for [n, d] matrices).  QT:
 // V and dO are one chunk's token-contiguous [B, d, C] buffers instead (read
 // MN-major), and the launch covers chunk cfix of every row only.
@@ -925,21 +924,24 @@ TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ 
   const int nks = (d + KR - 1) / KR;
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
-  Concat<DmaOpMN<T, G::NW, G::BP>> op;
-  std::conditional_t<QT, Concat<DmaOpMN<T, G::NW, G::BQ>>, Concat<DmaOp<G::NW, G::BQ>>> oq;
-  op.a.init(S + (int64_t)b * ssb + (int64_t)c * ssc + j0, min(G::BP, f - j0), ldf, d);
-  op.b.init(W + (int64_t)b * wsb + (int64_t)c * wsc + j0, min(G::BP, f - j0), ldf, d);
-  if constexpr (QT) {
-    const int64_t q0 = (int64_t)b * d * C_ + t0;               // chunk buffers [B, d, C]
-    oq.a.init(V + q0, min(G::BQ, C_ - t0), (uint64_t)C_ * esz<T>(), d);
-    oq.b.init(dO + q0, min(G::BQ, C_ - t0), (uint64_t)C_ * esz<T>(), d);
-  } else {
-    const uint64_t ldqb = (uint64_t)ldq * esz<T>();
-    oq.a.init(V + row0 * ldq, nullptr, min(G::BQ, C_ - t0), ldqb, (unsigned)ldd);
-    oq.b.init(dO + row0 * ldq, nullptr, min(G::BQ, C_ - t0), ldqb, (unsigned)ldd);
+  // stream 0: (S_j, eta V^_j); stream 1: (W_j, dO_j).  Each K loop ends on a
+  // barrier, so the second may refill the stages at once.
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    DmaOpMN<T, G::NW, G::BP> op;
+    std::conditional_t<QT, DmaOpMN<T, G::NW, G::BQ>, DmaOp<G::NW, G::BQ>> oq;
+    const T* Pm = st == 0 ? S + (int64_t)b * ssb + (int64_t)c * ssc : W + (int64_t)b * wsb + (int64_t)c * wsc;
+    const T* Qm = st == 0 ? V : dO;
+    op.init(Pm + j0, min(G::BP, f - j0), ldf, d);
+    if constexpr (QT) {
+      const int64_t q0 = (int64_t)b * d * C_ + t0;               // chunk buffers [B, d, C]
+      oq.init(Qm + q0, min(G::BQ, C_ - t0), (uint64_t)C_ * esz<T>(), d);
+    } else {
+      const uint64_t ldqb = (uint64_t)ldq * esz<T>();
+      oq.init(Qm + row0 * ldq, nullptr, min(G::BQ, C_ - t0), ldqb, (unsigned)ldd);
+    }
+    mainloop<T, G>(op, oq, nks, acc, smem, NoHook{});
   }
-  op.n1 = oq.n1 = nks;
-  mainloop<T, G>(op, oq, 2 * nks, acc, smem, NoHook{});
 
   const int tn = min(G::BQ, C_ - t0), jn = min(G::BP, f - j0);
   constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(T) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;

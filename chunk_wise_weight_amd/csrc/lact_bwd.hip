@@ -129,15 +129,19 @@ TTT_GEMM_KERNEL(Wide) void k_bgemm(BGemmSet set) {
     init_op<T, QMN, G::BQ>(oq, g.Q[0], b, q0, g.NQ, K0, k0);
     mainloop<T, G>(op, oq, (K0 + KR - 1) / KR, acc, smem, NoHook{});
   } else {
-    Concat<OpOf<T, PMN, G::BP>> op;
-    Concat<OpOf<T, QMN, G::BQ>> oq;
-    init_op<T, PMN, G::BP>(op.a, g.P[0], b, p0, g.NP, K0, k0);
-    init_op<T, QMN, G::BQ>(oq.a, g.Q[0], b, q0, g.NQ, K0, k0);
-    init_op<T, PMN, G::BP>(op.b, g.P[1], b, p0, g.NP, K1, k0);
-    init_op<T, QMN, G::BQ>(oq.b, g.Q[1], b, q0, g.NQ, K1, k0);
-    const int n1 = (K0 + KR - 1) / KR, n2 = (K1 + KR - 1) / KR;
-    op.n1 = oq.n1 = n1;
-    mainloop<T, G>(op, oq, n1 + n2, acc, smem, NoHook{});
+    // the two streams one after the other, each with its own operand state, so
+    // that only one stream's DMA offsets are live at a time (both at once spill);
+    // each K loop ends on a barrier, so the second may refill the stages at once
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int Ks = st == 0 ? K0 : K1;
+      if (Ks <= 0) continue;
+      OpOf<T, PMN, G::BP> op;
+      OpOf<T, QMN, G::BQ> oq;
+      init_op<T, PMN, G::BP>(op, g.P[st], b, p0, g.NP, Ks, k0);
+      init_op<T, QMN, G::BQ>(oq, g.Q[st], b, q0, g.NQ, Ks, k0);
+      mainloop<T, G>(op, oq, (Ks + KR - 1) / KR, acc, smem, NoHook{});
+    }
   }
 
   // out[q][p]: staged by rows q (p contiguous), in passes when a whole tile
