@@ -383,6 +383,18 @@ hipError_t bgemm(const BGemm& g, hipStream_t s) {
   return bgemm_set<T, PMN, QMN, NS, MODE>(set, s);
 }
 
+// Two GEMMs of one kind as one launch (twice the tiles of either: the short-K
+// products fill the GPU for two rounds instead of one).
+template <typename T, bool PMN, bool QMN, int NS, int MODE>
+hipError_t bgemm2(const BGemm& g0, const BGemm& g1, hipStream_t s) {
+  BGemmSet set{};
+  set.g[0] = g0;
+  set.g[1] = g1;
+  set.n = 2;
+  set.nsplit = 1;
+  return bgemm_set<T, PMN, QMN, NS, MODE>(set, s);
+}
+
 template <typename T, int STAGE>
 hipError_t ew(const EwArgs& a, int BH, hipStream_t s) {
   k_lact_ew<T, STAGE><<<dim3((unsigned)cdiv64(a.n / 8, 256), (unsigned)BH), 256, 0, s>>>(a);
@@ -511,8 +523,9 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     const BOp Qc{(const T*)a.q + (int64_t)c * C * dh, dh, Sn};
     const BOp dOc{(const T*)a.dO + (int64_t)c * C * dh, dh, Sn};
     hipError_t r;
-    if ((r = bgemm<T, false, false, 1, kStoreT>(one({W1, dh, S3}, Qc, dh, m, C, Aq, m, Scm), s)) != hipSuccess) return r;
-    if ((r = bgemm<T, false, false, 1, kStoreT>(one({W3, dh, S3}, Qc, dh, m, C, Uq, m, Scm), s)) != hipSuccess) return r;
+    if ((r = bgemm2<T, false, false, 1, kStoreT>(one({W1, dh, S3}, Qc, dh, m, C, Aq, m, Scm),
+                                                 one({W3, dh, S3}, Qc, dh, m, C, Uq, m, Scm), s)) != hipSuccess)
+      return r;
     if ((r = bgemm<T, true, false, 1, kStoreT>(one({W2, m, S3}, dOc, dh, m, C, dHq, m, Scm), s)) != hipSuccess) return r;
     EwArgs ea{Aq, Uq, dHq, nullptr, nullptr, nullptr, Hq, dAq, dUq, Scm};
     if ((r = ew<T, kEwQ>(ea, BH, s)) != hipSuccess) return r;
@@ -536,8 +549,9 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     k_lact_gscale<T><<<(unsigned)cdiv64((int64_t)BH * S3 / 4, 256), 256, 0, s>>>(g, gG, (int64_t)BH * S3, -a.eta);
     if ((r = hipGetLastError()) != hipSuccess) return r;
     // the forward's key pass at W
-    if ((r = bgemm<T, false, false, 1, kStoreT>(one({W1, dh, S3}, Kc, dh, m, C, A, m, Scm), s)) != hipSuccess) return r;
-    if ((r = bgemm<T, false, false, 1, kStoreT>(one({W3, dh, S3}, Kc, dh, m, C, U, m, Scm), s)) != hipSuccess) return r;
+    if ((r = bgemm2<T, false, false, 1, kStoreT>(one({W1, dh, S3}, Kc, dh, m, C, A, m, Scm),
+                                                 one({W3, dh, S3}, Kc, dh, m, C, U, m, Scm), s)) != hipSuccess)
+      return r;
     EwArgs eh{A, U, nullptr, nullptr, nullptr, nullptr, Hh, nullptr, nullptr, Scm};
     if ((r = ew<T, kEwH>(eh, BH, s)) != hipSuccess) return r;
     // R = Hh W2^T - v: Y into the fp32 partial, then the residual formed in fp32 as one rounding
@@ -550,8 +564,9 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     EwArgs ek{A, U, dH, nullptr, nullptr, nullptr, dA, dU, nullptr, Scm};
     if ((r = ew<T, kEwKey>(ek, BH, s)) != hipSuccess) return r;
     // through G1 = dA^T k, G3 = dU^T k
-    if ((r = bgemm<T, false, false, 1, kStoreT>(one({gG1, dh, S3}, Kc, dh, m, C, ddA, m, Scm), s)) != hipSuccess) return r;
-    if ((r = bgemm<T, false, false, 1, kStoreT>(one({gG3, dh, S3}, Kc, dh, m, C, ddU, m, Scm), s)) != hipSuccess) return r;
+    if ((r = bgemm2<T, false, false, 1, kStoreT>(one({gG1, dh, S3}, Kc, dh, m, C, ddA, m, Scm),
+                                                 one({gG3, dh, S3}, Kc, dh, m, C, ddU, m, Scm), s)) != hipSuccess)
+      return r;
     EwArgs ed{A, U, ddA, ddU, nullptr, nullptr, ddH, nullptr, nullptr, Scm};
     if ((r = ew<T, kEwDdh>(ed, BH, s)) != hipSuccess) return r;
     // dR = Hh gG2^T + ddH W2^T; dv = -dR
