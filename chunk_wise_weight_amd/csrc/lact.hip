@@ -83,11 +83,14 @@ __host__ __device__ constexpr int cdiv_d(int a, int b) { return (a + b - 1) / b;
 // A = X W1^T, U = X W3^T over the rows X of both parts.  P = W1 / W3 rows in
 // alternating 32-row blocks (128 hidden units per tile), Q = rows (tokens),
 // so that a lane holds 4 consecutive hidden units of one token.  Writes Hh
-// [2, BH, C, m] for both parts, and for the key part A and U [BH, C, m].
+// [2, BH, C, m] for both parts (part p of row bh at Hh + p hpart + bh C m),
+// and for the key part A and U [BH, C, m].  Row bh's W1 and W3 are at W1s +
+// bh wsb and W3s + bh wsb.
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ W1s,
                                        const T* __restrict__ W3s, T* __restrict__ Hh, T* __restrict__ A,
-                                       T* __restrict__ U, int BH, int n, int dh, int m, int C, StepRows sr) {
+                                       T* __restrict__ U, int BH, int n, int dh, int m, int C, StepRows sr,
+                                       int64_t wsb, int64_t hpart) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (m + G::BP / 2 - 1) / (G::BP / 2);
@@ -106,7 +109,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restr
   const int64_t md = (int64_t)m * dh;
 
   DmaOp<G::NW, G::BP, true> op;
-  op.init(W1s + bh * md + (int64_t)j0 * dh, W3s + bh * md + (int64_t)j0 * dh, min(G::BP / 2, m - j0), ldb,
+  op.init(W1s + bh * wsb + (int64_t)j0 * dh, W3s + bh * wsb + (int64_t)j0 * dh, min(G::BP / 2, m - j0), ldb,
           (unsigned)ldb);
   DmaOp<G::NW, G::BQ> oq;
   oq.init(X + (int64_t)r0 * dh, nullptr, min(G::BQ, nrows - r0), ldb, (unsigned)ldb);
@@ -183,12 +186,13 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restr
   }
   put(smem, H0{});
   __syncthreads();
-  flush(smem, Hh + ((int64_t)part * BH + bh) * C * m);
+  flush(smem, Hh + (int64_t)part * hpart + (int64_t)bh * C * m);
 }
 
 // ------------------------------------------------------------------ fwd2
 
-// Y = Hh W2^T.  P = dh rows of W2s [BH, dh, m], Q = rows of Hh (both parts).
+// Y = Hh W2^T.  P = dh rows of W2s (row bh's [dh, m] at W2s + bh wsb), Q =
+// rows of Hh (both parts, laid out as k_lact_fwd1 writes them).
 // Query rows: O[bh, qc C + r, :] = Y.  Key rows: R [BH, C, dh], the gradient of
 // the chunk loss with respect to the output -- Y - V for the squared error,
 // -V for the dot-product loss (loss_dot) -- times the token's learning rate
@@ -196,7 +200,8 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restr
 template <typename T>
 TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __restrict__ W2s, const T* __restrict__ v,
                                        T* __restrict__ O, T* __restrict__ R, int BH, int n, int dh, int m, int C,
-                                       StepRows sr, const float* __restrict__ eta_tok, int loss_dot) {
+                                       StepRows sr, const float* __restrict__ eta_tok, int loss_dot, int64_t wsb,
+                                       int64_t hpart) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (dh + G::BP - 1) / G::BP;
@@ -214,8 +219,9 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __rest
 
   DmaOp<G::NW, G::BP> op;
   DmaOp<G::NW, G::BQ> oq;
-  op.init(W2s + (int64_t)bh * dh * m + (int64_t)i0 * m, nullptr, min(G::BP, dh - i0), ldb, (unsigned)ldb);
-  oq.init(Hh + (((int64_t)part * BH + bh) * C + r0) * m, nullptr, min(G::BQ, nrows - r0), ldb, (unsigned)ldb);
+  op.init(W2s + (int64_t)bh * wsb + (int64_t)i0 * m, nullptr, min(G::BP, dh - i0), ldb, (unsigned)ldb);
+  oq.init(Hh + (int64_t)part * hpart + ((int64_t)bh * C + r0) * m, nullptr, min(G::BQ, nrows - r0), ldb,
+          (unsigned)ldb);
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
   mainloop<T, G>(op, oq, (int)((ldb + 127) / 128), acc, smem, NoHook{});
@@ -744,13 +750,15 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
       continue;
     }
     const int tq1 = (int)(cdiv(sr.nq, Wide::BQ) + cdiv(sr.nk, Wide::BQ));
-    if (want()) k_lact_fwd1<T><<<(unsigned)(cdiv(m, Wide::BP / 2) * tq1 * BH), Wide::NT, 0, s>>>(q, kk, W1s, W3s, Hh, A, U, BH, n,
-                                                                                   dh, m, C, sr);
+    const int64_t hpart = (int64_t)BH * C * m;
+    if (want())
+      k_lact_fwd1<T><<<(unsigned)(cdiv(m, Wide::BP / 2) * tq1 * BH), Wide::NT, 0, s>>>(q, kk, W1s, W3s, Hh, A, U, BH,
+                                                                                     n, dh, m, C, sr, md, hpart);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int tq2 = (int)(cdiv(sr.nq, Wide::BQ) + cdiv(sr.nk, Wide::BQ));
     if (want())
       k_lact_fwd2<T><<<(unsigned)(cdiv(dh, Wide::BP) * tq2 * BH), Wide::NT, 0, s>>>(Hh, W2s, v, O, R, BH, n, dh, m, C,
-                                                                                 sr, eta_tok, a.loss_dot);
+                                                                                 sr, eta_tok, a.loss_dot, md, hpart);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (sr.nk == 0) {
       if (passes && (e = keep_slot(sr.kc + 1)) != hipSuccess) return e;
@@ -800,6 +808,29 @@ hipError_t enqueue_lact_group(const LactArgs& a, int bh0, int BH, char* wsg, hip
 
 }  // namespace
 
+// The backward's passes over one chunk's rows X (keys or queries of chunk c)
+// with the states at W (row bh's W1, W3, W2 at W + bh wsb + 0, m dh, 2 m dh):
+// A, U and Hh = silu(A) U (all [BH, C, m]); and R = Hh W2^T - v (squared
+// error, rounded once) [BH, C, dh].
+template <typename T>
+hipError_t launch_lact_gate_pass(const T* X, const T* W, int64_t wsb, T* A, T* U, T* Hh, int BH, int n, int dh,
+                                 int m, int C, int c, hipStream_t s) {
+  const StepRows sr{0, C, 0, c};
+  const int64_t md = (int64_t)m * dh;
+  k_lact_fwd1<T><<<(unsigned)(cdiv(m, Wide::BP / 2) * cdiv(C, Wide::BQ) * BH), Wide::NT, 0, s>>>(
+      X, X, W, W + md, Hh, A, U, BH, n, dh, m, C, sr, wsb, 0);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_lact_residual_pass(const T* Hh, const T* W, int64_t wsb, const T* v, T* R, int BH, int n, int dh,
+                                     int m, int C, int c, hipStream_t s) {
+  const StepRows sr{0, C, 0, c};
+  k_lact_fwd2<T><<<(unsigned)(cdiv(dh, Wide::BP) * cdiv(C, Wide::BQ) * BH), Wide::NT, 0, s>>>(
+      Hh, W + 2 * (int64_t)m * dh, v, nullptr, R, BH, n, dh, m, C, sr, nullptr, 0, wsb, 0);
+  return hipGetLastError();
+}
+
 // Without a side stream the rows run as one chain on s.  With one, group 0
 // runs on s and group 1 on the side stream, between the fork event recorded
 // on s (after group 0's lead) and the join event that s waits for, so that the
@@ -835,5 +866,13 @@ template size_t lact_workspace_bytes<float>(int, int, int, int, int, int);
 template size_t lact_workspace_bytes<bf16>(int, int, int, int, int, int);
 template hipError_t launch_lact<float>(const LactArgs&, hipStream_t);
 template hipError_t launch_lact<bf16>(const LactArgs&, hipStream_t);
+#define TTT_LACT_PASSES(T)                                                                                          \
+  template hipError_t launch_lact_gate_pass<T>(const T*, const T*, int64_t, T*, T*, T*, int, int, int, int, int,  \
+                                               int, hipStream_t);                                                 \
+  template hipError_t launch_lact_residual_pass<T>(const T*, const T*, int64_t, const T*, T*, int, int, int, int, \
+                                                   int, int, hipStream_t);
+TTT_LACT_PASSES(float)
+TTT_LACT_PASSES(bf16)
+#undef TTT_LACT_PASSES
 
 }  // namespace ttt

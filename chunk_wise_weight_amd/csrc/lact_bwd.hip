@@ -52,7 +52,19 @@ struct BOp {
   int64_t ld, bs;
 };
 
-enum { kStoreT = 0, kStoreF32 = 1, kAccF32 = 2, kAddF32ToT = 3 };
+// Output modes.  The gate modes finish an elementwise stage in the epilogue
+// from the tile's fp32 values x and inputs in[] read at the same positions
+// (layout of out), with s the logistic of A, S = silu(A) = A s and
+// silu'(A) = s (1 + A (1 - s)):
+//   kGateKey: out = dH = x;  eo0 = dA = x U silu'(A), eo1 = dU = x S
+//             (in: A, U)
+//   kGateQ:   x = dHq (not stored);  eo0 = dAq = x U silu'(A), eo1 = dUq = x S
+//             (in: Aq, Uq)
+//   kGateF:   x = dHh (not stored);  eo0 = dA_f = ddA dH U silu''(A) + (ddU dH +
+//             x U) silu'(A), eo1 = dU_f = ddA dH silu'(A) + x S
+//             (in: A, U, dH, ddA, ddU)
+//   kStoreNeg: out = x and eo0 = -x (eo0 rows ldo apart, batch stride eo_so)
+enum { kStoreT = 0, kStoreF32 = 1, kAccF32 = 2, kAddF32ToT = 3, kGateKey = 4, kGateQ = 5, kGateF = 6, kStoreNeg = 7 };
 
 struct BGemm {
   BOp P[2], Q[2];
@@ -63,6 +75,9 @@ struct BGemm {
   const float* add;  // kAddF32ToT: out = alpha acc + add, add[b][q][p] at add + b add_so + q ldo + p
   int64_t add_so;
   float alpha;
+  const void* in[5];  // the gate modes' inputs (dtype, layout of out)
+  void* eo[2];        // the gate modes' and kStoreNeg's extra outputs (dtype)
+  int64_t eo_so;      // kStoreNeg: batch stride of eo[0]
 };
 
 // Up to three GEMMs of one kind in one launch (their tiles one after the
@@ -147,6 +162,7 @@ TTT_GEMM_KERNEL(Wide) void k_bgemm(BGemmSet set) {
   // out[q][p]: staged by rows q (p contiguous), in passes when a whole tile
   // does not fit the stage area
   using TO = std::conditional_t<MODE == kStoreF32 || MODE == kAccF32, float, T>;
+  constexpr bool GATE = MODE == kGateKey || MODE == kGateQ || MODE == kGateF;
   constexpr int PASSES = (G::BQ * G::BP * (int)sizeof(float) + G::Smem - 1) / G::Smem, RPP = G::BQ / PASSES;
   const Staged<float, G::BP> st{smem};
   const int qn = min(G::BQ, g.NQ - q0), pn = min(G::BP, g.NP - p0);
@@ -165,15 +181,76 @@ TTT_GEMM_KERNEL(Wide) void k_bgemm(BGemmSet set) {
     }
     __syncthreads();
     const int rows = max(0, min(RPP, qn - ps * RPP));
-    constexpr int SPANS = G::BP / 4;               // 4-element spans per staged row
-    for (int idx = threadIdx.x; idx < rows * SPANS; idx += G::NT) {
-      const int r = idx / SPANS, c = (idx - r * SPANS) * 4;
-      if (c >= pn) continue;                        // NP % 4 == 0
-      const int64_t o = (int64_t)(q0 + ps * RPP + r) * g.ldo + p0 + c;
-      f32x4 v = *reinterpret_cast<const f32x4*>(smem + st.off(r, c));
-      if constexpr (MODE == kAccF32) v += load4(out + o);
-      if constexpr (MODE == kAddF32ToT) v += load4(add + o);
-      store4(out + o, v[0], v[1], v[2], v[3]);
+    if constexpr (GATE) {
+      // 8-element spans (16-byte reads of bf16 inputs); the gate modes' outputs are [C, m] tiles, m % 8 == 0
+      constexpr int SPANS = G::BP / 8;
+      for (int idx = threadIdx.x; idx < rows * SPANS; idx += G::NT) {
+        const int r = idx / SPANS, c = (idx - r * SPANS) * 8;
+        if (c >= pn) continue;
+        const int64_t o = (int64_t)(q0 + ps * RPP + r) * g.ldo + p0 + c;
+        const int64_t e = (int64_t)b * g.so + o;
+        float x[8], A[8], U[8], dH[8], ddA[8], ddU[8], y0[8], y1[8];
+        {
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(smem + st.off(r, c));
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(smem + st.off(r, c + 4));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[i] = v0[i];
+            x[4 + i] = v1[i];
+          }
+        }
+        auto in8 = [&](int i, float* d) {
+          const T* p = (const T*)g.in[i] + e;
+          const f32x4 a0 = load4(p), a1 = load4(p + 4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            d[j] = a0[j];
+            d[4 + j] = a1[j];
+          }
+        };
+        in8(0, A);
+        in8(1, U);
+        if constexpr (MODE == kGateF) {
+          in8(2, dH);
+          in8(3, ddA);
+          in8(4, ddU);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float sg = sigmoid_f(A[i]), S = A[i] * sg, s1 = sg * (1.0f + A[i] * (1.0f - sg));
+          if constexpr (MODE == kGateF) {
+            const float s2 = sg * (1.0f - sg) * (2.0f + A[i] * (1.0f - 2.0f * sg));
+            y0[i] = ddA[i] * dH[i] * U[i] * s2 + (ddU[i] * dH[i] + x[i] * U[i]) * s1;
+            y1[i] = ddA[i] * dH[i] * s1 + x[i] * S;
+          } else {
+            y0[i] = x[i] * U[i] * s1;
+            y1[i] = x[i] * S;
+          }
+        }
+        T* e0 = (T*)g.eo[0] + e;
+        T* e1 = (T*)g.eo[1] + e;
+        store4(e0, y0[0], y0[1], y0[2], y0[3]);
+        store4(e0 + 4, y0[4], y0[5], y0[6], y0[7]);
+        store4(e1, y1[0], y1[1], y1[2], y1[3]);
+        store4(e1 + 4, y1[4], y1[5], y1[6], y1[7]);
+        if constexpr (MODE == kGateKey) {
+          store4(out + o, x[0], x[1], x[2], x[3]);
+          store4(out + o + 4, x[4], x[5], x[6], x[7]);
+        }
+      }
+    } else {
+      constexpr int SPANS = G::BP / 4;             // 4-element spans per staged row
+      for (int idx = threadIdx.x; idx < rows * SPANS; idx += G::NT) {
+        const int r = idx / SPANS, c = (idx - r * SPANS) * 4;
+        if (c >= pn) continue;                      // NP % 4 == 0
+        const int64_t o = (int64_t)(q0 + ps * RPP + r) * g.ldo + p0 + c;
+        f32x4 v = *reinterpret_cast<const f32x4*>(smem + st.off(r, c));
+        if constexpr (MODE == kAccF32) v += load4(out + o);
+        if constexpr (MODE == kAddF32ToT) v += load4(add + o);
+        store4(out + o, v[0], v[1], v[2], v[3]);
+        if constexpr (MODE == kStoreNeg)
+          store4((T*)g.eo[0] + (int64_t)b * g.eo_so + o, -v[0], -v[1], -v[2], -v[3]);
+      }
     }
     __syncthreads();
   }
@@ -181,24 +258,17 @@ TTT_GEMM_KERNEL(Wide) void k_bgemm(BGemmSet set) {
 
 // ---------------------------------------------------------------- elementwise gate terms
 
-enum { kEwH = 0, kEwKey = 1, kEwDdh = 2, kEwF = 3, kEwQ = 4 };
-
 struct EwArgs {
-  const void *A, *U, *x1, *x2, *x3, *x4;   // inputs beside A and U (by stage)
-  void *y1, *y2, *y3;                      // outputs
-  int64_t n;                               // elements per row group (C m)
+  const void *A, *U, *ddA, *ddU;   // [BH, C, m] each (contiguous)
+  void* ddH;
+  int64_t n;                       // elements per row group (C m)
 };
 
-// Eight consecutive elements per thread of [BH, C, m] buffers (contiguous):
-//   kEwH:   y1 = Hh = silu(A) U
-//   kEwKey: x1 = dH;                 y1 = dA = dH U silu'(A), y2 = dU = dH silu(A)
-//   kEwDdh: x1 = ddA, x2 = ddU;      y1 = ddH = ddA U silu'(A) + ddU silu(A)
-//   kEwF:   x1 = dH, x2 = ddA, x3 = ddU, x4 = dHh;
-//           y1 = dA_f = ddA dH U silu''(A) + (ddU dH + dHh U) silu'(A),
-//           y2 = dU_f = ddA dH silu'(A) + dHh silu(A)
-//   kEwQ:   (A, U = Aq, Uq) x1 = dHq; y1 = Hq, y2 = dAq, y3 = dUq
-template <typename T, int STAGE>
-__global__ __launch_bounds__(256) void k_lact_ew(EwArgs a) {
+// ddH = ddA U silu'(A) + ddU silu(A), eight consecutive elements per thread
+// (the one gate stage that needs two GEMMs' outputs at once; the others are
+// formed in the epilogue of the GEMM that produces their input).
+template <typename T>
+__global__ __launch_bounds__(256) void k_lact_ddh(EwArgs a) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (e >= a.n) return;
   const int64_t o = (int64_t)blockIdx.y * a.n + e;
@@ -211,57 +281,19 @@ __global__ __launch_bounds__(256) void k_lact_ew(EwArgs a) {
       v[4 + i] = x1[i];
     }
   };
-  auto st8 = [&](void* p, const float* v) {
-    T* t = (T*)p + o;
-    store4(t, v[0], v[1], v[2], v[3]);
-    store4(t + 4, v[4], v[5], v[6], v[7]);
-  };
-  float A[8], U[8], x1[8], x2[8], x3[8], x4[8], y1[8], y2[8], y3[8];
+  float A[8], U[8], x1[8], x2[8], y[8];
   ld8(a.A, A);
   ld8(a.U, U);
-  if constexpr (STAGE != kEwH) ld8(a.x1, x1);
-  if constexpr (STAGE == kEwDdh || STAGE == kEwF) ld8(a.x2, x2);
-  if constexpr (STAGE == kEwF) {
-    ld8(a.x3, x3);
-    ld8(a.x4, x4);
-  }
+  ld8(a.ddA, x1);
+  ld8(a.ddU, x2);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const float s = sigmoid_f(A[i]);
-    const float S = A[i] * s;                             // silu(A)
-    const float s1 = s * (1.0f + A[i] * (1.0f - s));      // silu'(A)
-    if constexpr (STAGE == kEwH) {
-      y1[i] = S * U[i];
-    } else if constexpr (STAGE == kEwKey) {
-      y1[i] = x1[i] * U[i] * s1;
-      y2[i] = x1[i] * S;
-    } else if constexpr (STAGE == kEwDdh) {
-      y1[i] = x1[i] * U[i] * s1 + x2[i] * S;
-    } else if constexpr (STAGE == kEwF) {
-      const float s2 = s * (1.0f - s) * (2.0f + A[i] * (1.0f - 2.0f * s));   // silu''(A)
-      y1[i] = x2[i] * x1[i] * U[i] * s2 + (x3[i] * x1[i] + x4[i] * U[i]) * s1;
-      y2[i] = x2[i] * x1[i] * s1 + x4[i] * S;
-    } else {
-      y1[i] = S * U[i];
-      y2[i] = x1[i] * U[i] * s1;
-      y3[i] = x1[i] * S;
-    }
+    y[i] = x1[i] * U[i] * s * (1.0f + A[i] * (1.0f - s)) + x2[i] * A[i] * s;
   }
-  st8(a.y1, y1);
-  if constexpr (STAGE == kEwKey || STAGE == kEwF || STAGE == kEwQ) st8(a.y2, y2);
-  if constexpr (STAGE == kEwQ) st8(a.y3, y3);
-}
-
-// dst[bh][t][j] = -src[bh][t][j] for one chunk: src [BH, C, dh] contiguous, dst
-// rows of [BH, n, dh] at the chunk's offset (dst already offset; row group stride
-// dstride); four elements per thread.
-template <typename T>
-__global__ __launch_bounds__(256) void k_lact_neg(const T* __restrict__ src, T* __restrict__ dst, int64_t n,
-                                                  int64_t dstride) {
-  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e >= n) return;
-  const f32x4 x = load4(src + (int64_t)blockIdx.y * n + e);
-  store4(dst + (int64_t)blockIdx.y * dstride + e, -x[0], -x[1], -x[2], -x[3]);
+  T* t = (T*)a.ddH + o;
+  store4(t, y[0], y[1], y[2], y[3]);
+  store4(t + 4, y[4], y[5], y[6], y[7]);
 }
 
 // dst[bh][t][j] = 0 for one chunk's rows of a [BH, n, dh] buffer (dst already
@@ -273,17 +305,6 @@ __global__ __launch_bounds__(256) void k_lact_zero_rows(T* __restrict__ dst, int
   store4(dst + (int64_t)blockIdx.y * dstride + e, 0.f, 0.f, 0.f, 0.f);
 }
 
-// R = Y - v for one chunk, formed in fp32 and rounded once: Y [BH, C, dh] fp32,
-// v rows of [BH, n, dh] at the chunk's offset (row group stride vstride), R
-// [BH, C, dh]; four elements per thread.
-template <typename T>
-__global__ __launch_bounds__(256) void k_lact_residual(const float* __restrict__ Y, const T* __restrict__ v,
-                                                       T* __restrict__ R, int64_t n, int64_t vstride) {
-  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (e >= n) return;
-  const f32x4 x = load4(Y + (int64_t)blockIdx.y * n + e) - load4(v + (int64_t)blockIdx.y * vstride + e);
-  store4(R + (int64_t)blockIdx.y * n + e, x[0], x[1], x[2], x[3]);
-}
 
 // gG = scale * g over the [BH, 3, m dh] gradients (operand dtype), four per thread.
 template <typename T>
@@ -331,7 +352,7 @@ __global__ __launch_bounds__(256) void k_lact_gsum(const float* __restrict__ g, 
 constexpr int kGradSplit = 4;
 
 struct LactBwdWs {
-  size_t fwd, keep, g, gG, cm[18], cd[2], part, gpart, total;
+  size_t fwd, keep, g, gG, cm[16], cd[2], part, gpart, total;
 };
 
 template <typename T>
@@ -347,7 +368,7 @@ LactBwdWs lact_bwd_layout(int B, int H, int n, int dh, int m, int C) {
   o += al256(BH * 3 * md * 4);
   w.gG = o;
   o += al256(BH * 3 * md * e);
-  for (int i = 0; i < 18; ++i) {
+  for (int i = 0; i < 16; ++i) {
     w.cm[i] = o;
     o += al256(BH * (size_t)C * m * e);
   }
@@ -395,9 +416,9 @@ hipError_t bgemm2(const BGemm& g0, const BGemm& g1, hipStream_t s) {
   return bgemm_set<T, PMN, QMN, NS, MODE>(set, s);
 }
 
-template <typename T, int STAGE>
-hipError_t ew(const EwArgs& a, int BH, hipStream_t s) {
-  k_lact_ew<T, STAGE><<<dim3((unsigned)cdiv64(a.n / 8, 256), (unsigned)BH), 256, 0, s>>>(a);
+template <typename T>
+hipError_t ddh(const EwArgs& a, int BH, hipStream_t s) {
+  k_lact_ddh<T><<<dim3((unsigned)cdiv64(a.n / 8, 256), (unsigned)BH), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -450,8 +471,8 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
   }
   const int k = C > 0 ? n / C : 0;
   const T* keep = (const T*)(a.ws + L.keep);
-  T* cm[18];
-  for (int i = 0; i < 18; ++i) cm[i] = (T*)(a.ws + L.cm[i]);
+  T* cm[16];
+  for (int i = 0; i < 16; ++i) cm[i] = (T*)(a.ws + L.cm[i]);
   T* A = cm[0];
   T* U = cm[1];
   T* Hh = cm[2];
@@ -461,15 +482,13 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
   T* ddA = cm[6];
   T* ddU = cm[7];
   T* ddH = cm[8];
-  T* dHh = cm[9];
-  T* dAf = cm[10];
-  T* dUf = cm[11];
-  T* Aq = cm[12];
-  T* Uq = cm[13];
-  T* Hq = cm[14];
-  T* dHq = cm[15];
-  T* dAq = cm[16];
-  T* dUq = cm[17];
+  T* dAf = cm[9];
+  T* dUf = cm[10];
+  T* Aq = cm[11];
+  T* Uq = cm[12];
+  T* Hq = cm[13];
+  T* dAq = cm[14];
+  T* dUq = cm[15];
   T* R = (T*)(a.ws + L.cd[0]);
   T* dR = (T*)(a.ws + L.cd[1]);
   float* part = (float*)(a.ws + L.part);
@@ -523,12 +542,16 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     const BOp Qc{(const T*)a.q + (int64_t)c * C * dh, dh, Sn};
     const BOp dOc{(const T*)a.dO + (int64_t)c * C * dh, dh, Sn};
     hipError_t r;
-    if ((r = bgemm2<T, false, false, 1, kStoreT>(one({W1, dh, S3}, Qc, dh, m, C, Aq, m, Scm),
-                                                 one({W3, dh, S3}, Qc, dh, m, C, Uq, m, Scm), s)) != hipSuccess)
-      return r;
-    if ((r = bgemm<T, true, false, 1, kStoreT>(one({W2, m, S3}, dOc, dh, m, C, dHq, m, Scm), s)) != hipSuccess) return r;
-    EwArgs ea{Aq, Uq, dHq, nullptr, nullptr, nullptr, Hq, dAq, dUq, Scm};
-    if ((r = ew<T, kEwQ>(ea, BH, s)) != hipSuccess) return r;
+    // Aq, Uq and Hq by the forward's gate kernel; dHq = dO W2 with dAq, dUq formed in its epilogue
+    if ((r = launch_lact_gate_pass<T>((const T*)a.q, W, S3, Aq, Uq, Hq, BH, n, dh, m, C, c, s)) != hipSuccess) return r;
+    {
+      BGemm gq = one({W2, m, S3}, dOc, dh, m, C, dAq, m, Scm);
+      gq.in[0] = Aq;
+      gq.in[1] = Uq;
+      gq.eo[0] = dAq;
+      gq.eo[1] = dUq;
+      if ((r = bgemm<T, true, false, 1, kGateQ>(gq, s)) != hipSuccess) return r;
+    }
     // g2 += dO^T Hq, g1 += dAq^T Q, g3 += dUq^T Q
     r = grad_set([&](const BGemmSet& set) { return bgemm_set<T, true, true, 1, kStoreF32>(set, s); },
                  one(cmK(Hq), dOc, C, m, dh, gpart + 2 * md, m, S3), one(Qc, cmK(dAq), C, dh, m, gpart, dh, S3),
@@ -548,40 +571,43 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     hipError_t r;
     k_lact_gscale<T><<<(unsigned)cdiv64((int64_t)BH * S3 / 4, 256), 256, 0, s>>>(g, gG, (int64_t)BH * S3, -a.eta);
     if ((r = hipGetLastError()) != hipSuccess) return r;
-    // the forward's key pass at W
-    if ((r = bgemm2<T, false, false, 1, kStoreT>(one({W1, dh, S3}, Kc, dh, m, C, A, m, Scm),
-                                                 one({W3, dh, S3}, Kc, dh, m, C, U, m, Scm), s)) != hipSuccess)
+    // the forward's key pass at W: A, U, Hh by its gate kernel, R = Hh W2^T - v by its residual kernel (formed in
+    // fp32, rounded once), then dH = R W2 with dA, dU formed in the epilogue
+    if ((r = launch_lact_gate_pass<T>((const T*)a.k, W, S3, A, U, Hh, BH, n, dh, m, C, c, s)) != hipSuccess) return r;
+    if ((r = launch_lact_residual_pass<T>(Hh, W, S3, (const T*)a.v, R, BH, n, dh, m, C, c, s)) != hipSuccess)
       return r;
-    EwArgs eh{A, U, nullptr, nullptr, nullptr, nullptr, Hh, nullptr, nullptr, Scm};
-    if ((r = ew<T, kEwH>(eh, BH, s)) != hipSuccess) return r;
-    // R = Hh W2^T - v: Y into the fp32 partial, then the residual formed in fp32 as one rounding
-    if ((r = bgemm<T, false, false, 1, kStoreF32>(one({W2, m, S3}, cmK(Hh), m, dh, C, part, dh, Scd), s)) != hipSuccess)
-      return r;
-    k_lact_residual<T><<<dim3((unsigned)cdiv64(Scd / 4, 256), (unsigned)BH), 256, 0, s>>>(
-        part, (const T*)a.v + (int64_t)c * C * dh, R, Scd, Sn);
-    if ((r = hipGetLastError()) != hipSuccess) return r;
-    if ((r = bgemm<T, true, false, 1, kStoreT>(one({W2, m, S3}, cdK(R), dh, m, C, dH, m, Scm), s)) != hipSuccess) return r;
-    EwArgs ek{A, U, dH, nullptr, nullptr, nullptr, dA, dU, nullptr, Scm};
-    if ((r = ew<T, kEwKey>(ek, BH, s)) != hipSuccess) return r;
+    {
+      BGemm gk = one({W2, m, S3}, cdK(R), dh, m, C, dH, m, Scm);
+      gk.in[0] = A;
+      gk.in[1] = U;
+      gk.eo[0] = dA;
+      gk.eo[1] = dU;
+      if ((r = bgemm<T, true, false, 1, kGateKey>(gk, s)) != hipSuccess) return r;
+    }
     // through G1 = dA^T k, G3 = dU^T k
     if ((r = bgemm2<T, false, false, 1, kStoreT>(one({gG1, dh, S3}, Kc, dh, m, C, ddA, m, Scm),
                                                  one({gG3, dh, S3}, Kc, dh, m, C, ddU, m, Scm), s)) != hipSuccess)
       return r;
-    EwArgs ed{A, U, ddA, ddU, nullptr, nullptr, ddH, nullptr, nullptr, Scm};
-    if ((r = ew<T, kEwDdh>(ed, BH, s)) != hipSuccess) return r;
-    // dR = Hh gG2^T + ddH W2^T; dv = -dR
-    if ((r = bgemm<T, false, false, 2, kStoreT>(
-             two(one({gG2, m, S3}, cmK(Hh), m, dh, C, dR, dh, Scd), {W2, m, S3}, cmK(ddH), m), s)) != hipSuccess)
-      return r;
-    k_lact_neg<T><<<dim3((unsigned)cdiv64(Scd / 4, 256), (unsigned)BH), 256, 0, s>>>(
-        dR, (T*)a.dv + (int64_t)c * C * dh, Scd, Sn);
-    if ((r = hipGetLastError()) != hipSuccess) return r;
-    // dHh = R gG2 + dR W2
-    if ((r = bgemm<T, true, false, 2, kStoreT>(
-             two(one({gG2, m, S3}, cdK(R), dh, m, C, dHh, m, Scm), {W2, m, S3}, cdK(dR), dh), s)) != hipSuccess)
-      return r;
-    EwArgs ef{A, U, dH, ddA, ddU, dHh, dAf, dUf, nullptr, Scm};
-    if ((r = ew<T, kEwF>(ef, BH, s)) != hipSuccess) return r;
+    if ((r = ddh<T>(EwArgs{A, U, ddA, ddU, ddH, Scm}, BH, s)) != hipSuccess) return r;
+    // dR = Hh gG2^T + ddH W2^T, and dv = -dR from the same epilogue
+    {
+      BGemm gr = two(one({gG2, m, S3}, cmK(Hh), m, dh, C, dR, dh, Scd), {W2, m, S3}, cmK(ddH), m);
+      gr.eo[0] = (T*)a.dv + (int64_t)c * C * dh;
+      gr.eo_so = Sn;
+      if ((r = bgemm<T, false, false, 2, kStoreNeg>(gr, s)) != hipSuccess) return r;
+    }
+    // dHh = R gG2 + dR W2, never stored: dA_f and dU_f formed in the epilogue
+    {
+      BGemm gf = two(one({gG2, m, S3}, cdK(R), dh, m, C, dAf, m, Scm), {W2, m, S3}, cdK(dR), dh);
+      gf.in[0] = A;
+      gf.in[1] = U;
+      gf.in[2] = dH;
+      gf.in[3] = ddA;
+      gf.in[4] = ddU;
+      gf.eo[0] = dAf;
+      gf.eo[1] = dUf;
+      if ((r = bgemm<T, true, false, 2, kGateF>(gf, s)) != hipSuccess) return r;
+    }
     // dk = (dA gG1 + dU gG3) + (dA_f W1 + dU_f W3), the first pair in fp32
     if ((r = bgemm<T, true, false, 2, kStoreF32>(
              two(one({gG1, dh, S3}, cmK(dA), m, dh, C, part, dh, Scd), {gG3, dh, S3}, cmK(dU), m), s)) != hipSuccess)

@@ -179,6 +179,15 @@ struct LactBwdArgs {
 };
 template <typename T>
 hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s);
+// The forward's key-side kernels on one chunk's rows X (keys or queries of chunk c of [BH, n, dh]) with states W
+// (row bh's W1, W3, W2 at W + bh wsb + 0, m dh, 2 m dh): A, U, Hh = silu(A) U [BH, C, m]; R = Hh W2^T - v
+// [BH, C, dh] (v rows of chunk c of [BH, n, dh]).
+template <typename T>
+hipError_t launch_lact_gate_pass(const T* X, const T* W, int64_t wsb, T* A, T* U, T* Hh, int BH, int n, int dh,
+                                 int m, int C, int c, hipStream_t s);
+template <typename T>
+hipError_t launch_lact_residual_pass(const T* Hh, const T* W, int64_t wsb, const T* v, T* R, int BH, int n, int dh,
+                                     int m, int C, int c, hipStream_t s);
 template <typename T>
 size_t lact_workspace_bytes(int B, int H, int n, int dh, int m, int C);
 template <typename T>

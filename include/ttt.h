@@ -601,7 +601,7 @@ int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta,
 /* Workspace bytes for ttt_lact_swiglu_backward: the forward's own
  * (ttt_lact_workspace_bytes), every chunk's state ((n / chunk + 1) B H 3 m dh
  * dtype), the state gradient (3 B H m dh fp32 and a dtype copy) and the
- * per-chunk intermediates (18 B H chunk m and 2 B H chunk dh dtype, B H chunk
+ * per-chunk intermediates (16 B H chunk m and 2 B H chunk dh dtype, B H chunk
  * dh fp32). */
 int ttt_lact_backward_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* bytes);
 
@@ -620,8 +620,9 @@ int ttt_lact_backward_workspace_bytes(const ttt_lact_shape* shape, int dtype, si
  * kernels (keys only) and keeps them in the workspace, then runs the chunks
  * from the last back: the query apply's backward with the state it saw (after
  * the chunk's update, or before it in TTT_APPLY_THEN_UPDATE order) and the
- * update's backward, each a few batched engine GEMMs over the (batch, head)
- * rows and elementwise passes.  dtype, sizes and errors as for
+ * update's backward: the forward's gate and residual kernels on the chunk's
+ * rows, then batched engine GEMMs over the (batch, head) rows whose epilogues
+ * form the gate terms, and one elementwise pass.  dtype, sizes and errors as for
  * ttt_lact_swiglu; batch == 0 gives zero weight gradients, seq_len == 0 zero
  * weight gradients and nothing else. */
 int ttt_lact_swiglu_backward(const ttt_lact_shape* shape, int dtype, int order, float eta,
