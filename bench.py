@@ -208,10 +208,15 @@ def bench_generic(cfg, steps, warmup):
         grads = tuple(torch.empty(*shp, dtype=t, device="cuda") for shp, t in (
             ((B, Hh, n, dh), dt), ((B, Hh, n, dh), dt), ((B, Hh, n, dh), dt), ((Hh, m, dh), torch.float32),
             ((Hh, m, dh), torch.float32), ((Hh, dh, m), torch.float32)))
-        nbytes = cw.ttt_lact_backward_workspace_bytes(cw.LactShape(B, Hh, n, dh, m, cfg.chunk), dt)
+        Ws = None
+        if cfg.kept_states:        # the forward call keeps its states (untimed); the backward reads them
+            Ws = torch.empty(n // cfg.chunk + 1, B, Hh, 3, m * dh, dtype=dt, device="cuda")
+            cw.ttt_lact_swiglu(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta, cfg.order,
+                               W_states=Ws)
+        nbytes = cw.ttt_lact_backward_workspace_bytes(cw.LactShape(B, Hh, n, dh, m, cfg.chunk), dt, Ws is not None)
         ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device="cuda")
         call = lambda: cw.ttt_lact_swiglu_backward(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], dO, cfg.chunk,
-                                                   cfg.eta, cfg.order, grads=grads, workspace=ws)
+                                                   cfg.eta, cfg.order, grads=grads, workspace=ws, W_states=Ws)
     elif isinstance(cfg, ti.LactConfig):
         x = ti.lact_inputs(cfg)
         g = {k: v.cuda() for k, v in x.items()}
@@ -377,6 +382,7 @@ def main():
                                   "muon": cfg.muon})
         if cfg.backward:
             out["config"]["pass"] = "backward of the LaCT layer (dq, dk, dv and the initial weights' gradients)"
+            out["config"]["states"] = "kept by the forward call" if cfg.kept_states else "recomputed"
             out["metric"] = "LaCT-layer backward tokens/s at 256K ctx; % of bf16 MFMA peak"
     else:
         out["config"] = {"workload": cfg.name, "batch": cfg.batch, "seq_len": cfg.seq_len, "d_model": cfg.d_model,

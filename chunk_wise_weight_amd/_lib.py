@@ -36,7 +36,8 @@ class LayerOptions(ctypes.Structure):
 class LactOptions(ctypes.Structure):
     _fields_ = [("order", ctypes.c_int), ("update_mask", ctypes.c_void_p), ("eta_tok", ctypes.c_void_p),
                 ("loss", ctypes.c_int), ("weight_norm", ctypes.c_int), ("muon", ctypes.c_int),
-                ("side_stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p), ("join_event", ctypes.c_void_p)]
+                ("side_stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p), ("join_event", ctypes.c_void_p),
+                ("W_states", ctypes.c_void_p)]
 
 
 class LactSideStream:
@@ -119,6 +120,7 @@ _SIGNATURES = {
     "ttt_lact_swiglu_ex": (_I, [ctypes.POINTER(LactShape), _I, _F, _P, _P, _P, _P, _P, _P,
                                 ctypes.POINTER(LactOptions), _P, _P, _P, _P, _P, _S, _P]),
     "ttt_lact_backward_workspace_bytes": (_I, [ctypes.POINTER(LactShape), _I, ctypes.POINTER(_S)]),
+    "ttt_lact_backward_workspace_bytes_ex": (_I, [ctypes.POINTER(LactShape), _I, _I, ctypes.POINTER(_S)]),
     "ttt_lact_swiglu_backward": (_I, [ctypes.POINTER(LactShape), _I, _I, _F] + [_P] * 13 + [_P, _S, _P]),
     "ttt_lact_swiglu_backward_ex": (_I, [ctypes.POINTER(LactShape), _I, _F] + [_P] * 7 +
                                     [ctypes.POINTER(LactOptions)] + [_P] * 6 + [_P, _S, _P]),
@@ -640,14 +642,15 @@ def _host_flags(update_mask, n, chunk):
 
 def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_then_apply", O=None, finals=None,
                     workspace=None, update_mask=None, eta_tok=None, loss="mse", weight_norm=False, muon=False,
-                    side=None):
+                    side=None, W_states=None):
     """LaCT SwiGLU layer.  Returns (O [B, H, n, dh], W1_f, W3_f [B, H, m, dh], W2_f [B, H, dh, m]).
 
     Options (ttt_lact_swiglu_ex): update_mask, a host sequence of n // chunk flags (only the flagged chunks
     take the update step, every chunk is applied); eta_tok, per-token learning rates [B, H, n] fp32 on the
     device; loss, "mse" or "dot"; weight_norm, L2-normalise the weight rows after every update; muon, step
     along Muon(g) (Newton-Schulz orthogonalised gradients); side, a LactSideStream on the tensors' device to run
-    half of the (batch, head) rows on (None: one chain on the current stream)."""
+    half of the (batch, head) rows on (None: one chain on the current stream); W_states, a [n // chunk + 1, B, H, 3,
+    m * dh] tensor of the layer's dtype that receives every chunk's state for ttt_lact_swiglu_backward."""
     B, Hh, n, dh = q.shape
     m = W1.shape[1]
     dt, dev = q.dtype, q.device
@@ -670,7 +673,10 @@ def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_t
     ordc = _ORDERS[order] if isinstance(order, str) else int(order)
     if side is not None and side.device != dev:
         raise ValueError(f"the side stream is on {side.device}, the tensors on {dev}")
-    if update_mask is None and eta_tok is None and loss == "mse" and not weight_norm and not muon and side is None:
+    if W_states is not None:
+        _need(W_states, "W_states", (n // chunk + 1, B, Hh, 3, m * dh), dt, dev)
+    if (update_mask is None and eta_tok is None and loss == "mse" and not weight_norm and not muon and side is None
+            and W_states is None):
         _check(lib().ttt_lact_swiglu(ctypes.byref(shape), _dt(dt), ordc, float(eta), _ptr(q), _ptr(k), _ptr(v),
                                      _ptr(W1), _ptr(W3), _ptr(W2), _ptr(O), _ptr(W1f), _ptr(W3f), _ptr(W2f),
                                      _ptr(ws), nbytes, _stream(dev)), "ttt_lact_swiglu")
@@ -683,7 +689,7 @@ def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_t
     opts = LactOptions(ordc, ctypes.cast(mask, ctypes.c_void_p) if mask is not None else None,
                        ctypes.c_void_p(eta_tok.data_ptr()) if eta_tok is not None and eta_tok.numel() else None,
                        1 if loss == "dot" else 0, 1 if weight_norm else 0, 1 if muon else 0,
-                       *(side.handles() if side is not None else (None, None, None)))
+                       *(side.handles() if side is not None else (None, None, None)), _vp(W_states))
     _check(lib().ttt_lact_swiglu_ex(ctypes.byref(shape), _dt(dt), float(eta), _ptr(q), _ptr(k), _ptr(v), _ptr(W1),
                                     _ptr(W3), _ptr(W2), ctypes.byref(opts), _ptr(O), _ptr(W1f), _ptr(W3f),
                                     _ptr(W2f), _ptr(ws), nbytes, _stream(dev)),
@@ -691,19 +697,19 @@ def ttt_lact_swiglu(q, k, v, W1, W3, W2, chunk: int, eta: float, order="update_t
     return O, W1f, W3f, W2f
 
 
-def ttt_lact_backward_workspace_bytes(shape: LactShape, dtype: torch.dtype) -> int:
+def ttt_lact_backward_workspace_bytes(shape: LactShape, dtype: torch.dtype, saved_states=False) -> int:
     out = ctypes.c_size_t(0)
-    _check(lib().ttt_lact_backward_workspace_bytes(ctypes.byref(shape), _dt(dtype), ctypes.byref(out)),
-           "ttt_lact_backward_workspace_bytes")
+    _check(lib().ttt_lact_backward_workspace_bytes_ex(ctypes.byref(shape), _dt(dtype), int(bool(saved_states)),
+                                                      ctypes.byref(out)), "ttt_lact_backward_workspace_bytes_ex")
     return out.value
 
 
 def ttt_lact_swiglu_backward(q, k, v, W1, W3, W2, dO, chunk: int, eta: float, order="update_then_apply",
-                             grads=None, workspace=None, update_mask=None):
+                             grads=None, workspace=None, update_mask=None, W_states=None):
     """Backward of the LaCT layer (squared error, plain GD) given dO = dLoss/dO [B, H, n, dh]; update_mask, a host
-    sequence of n // chunk flags as the forward layer took it (through ttt_lact_swiglu_backward_ex).  Returns (dq,
-    dk, dv [B, H, n, dh] in the inputs' dtype, dW1, dW3 [H, m, dh], dW2 [H, dh, m] fp32, summed over the batch
-    rows)."""
+    sequence of n // chunk flags as the forward layer took it, and W_states, the states the forward call kept
+    (both through ttt_lact_swiglu_backward_ex).  Returns (dq, dk, dv [B, H, n, dh] in the inputs' dtype, dW1, dW3
+    [H, m, dh], dW2 [H, dh, m] fp32, summed over the batch rows)."""
     B, Hh, n, dh = q.shape
     m = W1.shape[1]
     dt, dev = q.dtype, q.device
@@ -718,12 +724,15 @@ def ttt_lact_swiglu_backward(q, k, v, W1, W3, W2, dO, chunk: int, eta: float, or
     for gt, (shp, t) in zip(grads, shapes):
         _need(gt, "gradient", shp, t, dev)
     shape = LactShape(B, Hh, n, dh, m, int(chunk))
-    nbytes = ttt_lact_backward_workspace_bytes(shape, dt)
+    if W_states is not None:
+        _need(W_states, "W_states", (n // chunk + 1, B, Hh, 3, m * dh), dt, dev)
+    nbytes = ttt_lact_backward_workspace_bytes(shape, dt, W_states is not None)
     ws = _workspace(nbytes, dev, workspace)
     ordc = _ORDERS[order] if isinstance(order, str) else int(order)
-    if update_mask is not None:
+    if update_mask is not None or W_states is not None:
         mask = _host_flags(update_mask, n, chunk)
-        opts = LactOptions(ordc, ctypes.cast(mask, ctypes.c_void_p), None, 0, 0, 0, None, None, None)
+        opts = LactOptions(ordc, ctypes.cast(mask, ctypes.c_void_p) if mask is not None else None, None, 0, 0, 0,
+                           None, None, None, _vp(W_states))
         _check(lib().ttt_lact_swiglu_backward_ex(ctypes.byref(shape), _dt(dt), float(eta), _ptr(q), _ptr(k),
                                                  _ptr(v), _ptr(W1), _ptr(W3), _ptr(W2), _ptr(dO), ctypes.byref(opts),
                                                  *[_ptr(g) for g in grads], _ptr(ws), nbytes, _stream(dev)),

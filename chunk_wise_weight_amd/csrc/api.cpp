@@ -1245,13 +1245,17 @@ int ttt_lact_swiglu(const ttt_lact_shape* shape, int dtype, int order, float eta
 }
 
 int ttt_lact_backward_workspace_bytes(const ttt_lact_shape* shape, int dtype, size_t* bytes) {
-  if (bytes == nullptr) return TTT_ERR_ARG;
+  return ttt_lact_backward_workspace_bytes_ex(shape, dtype, 0, bytes);
+}
+
+int ttt_lact_backward_workspace_bytes_ex(const ttt_lact_shape* shape, int dtype, int saved_states, size_t* bytes) {
+  if (bytes == nullptr || (saved_states != 0 && saved_states != 1)) return TTT_ERR_ARG;
   int st = check_lact(shape, dtype);
   if (st != TTT_OK) return st;
   const int B = (int)shape->batch, H = (int)shape->heads, n = (int)shape->seq_len, dh = (int)shape->head_dim,
             m = (int)shape->hidden, C = (int)shape->chunk;
-  *bytes = dtype == TTT_BF16 ? ttt::lact_bwd_workspace_bytes<bf16>(B, H, n, dh, m, C)
-                             : ttt::lact_bwd_workspace_bytes<float>(B, H, n, dh, m, C);
+  *bytes = dtype == TTT_BF16 ? ttt::lact_bwd_workspace_bytes<bf16>(B, H, n, dh, m, C, saved_states != 0)
+                             : ttt::lact_bwd_workspace_bytes<float>(B, H, n, dh, m, C, saved_states != 0);
   return TTT_OK;
 }
 
@@ -1288,8 +1292,10 @@ int ttt_lact_swiglu_backward_ex(const ttt_lact_shape* shape, int dtype, float et
   if ((int64_t)B * H * n > 0 && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(dO) || !ok_ptr(dq) ||
                                  !ok_ptr(dk) || !ok_ptr(dv)))
     return TTT_ERR_ARG;
-  const size_t need = dtype == TTT_BF16 ? ttt::lact_bwd_workspace_bytes<bf16>(B, H, n, dh, m, C)
-                                        : ttt::lact_bwd_workspace_bytes<float>(B, H, n, dh, m, C);
+  const bool saved = options->W_states != nullptr;
+  if (saved && !aligned16(options->W_states)) return TTT_ERR_ARG;
+  const size_t need = dtype == TTT_BF16 ? ttt::lact_bwd_workspace_bytes<bf16>(B, H, n, dh, m, C, saved)
+                                        : ttt::lact_bwd_workspace_bytes<float>(B, H, n, dh, m, C, saved);
   if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need)) return TTT_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (H == 0) return TTT_OK;
@@ -1301,7 +1307,7 @@ int ttt_lact_swiglu_backward_ex(const ttt_lact_shape* shape, int dtype, float et
     return r;
   }
   ttt::LactBwdArgs a{B, H, n, dh, m, C, order, eta, q, k, v, W1, W3, W2, dO, dq, dk, dv, dW1, dW3, dW2,
-                     (char*)workspace, options->update_mask};
+                     (char*)workspace, options->update_mask, options->W_states};
   return dev(dtype == TTT_BF16 ? ttt::launch_lact_backward<bf16>(a, s) : ttt::launch_lact_backward<float>(a, s));
 }
 
@@ -1317,6 +1323,7 @@ int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta, const 
   if (options->eta_tok != nullptr && !ok_ptr(options->eta_tok)) return TTT_ERR_ARG;
   if (options->side_stream != nullptr && (options->fork_event == nullptr || options->join_event == nullptr))
     return TTT_ERR_ARG;
+  if (options->W_states != nullptr && !aligned16(options->W_states)) return TTT_ERR_ARG;
   int st = check_lact(shape, dtype);
   if (st != TTT_OK) return st;
   if (order != TTT_UPDATE_THEN_APPLY && order != TTT_APPLY_THEN_UPDATE) return TTT_ERR_ARG;
@@ -1334,6 +1341,7 @@ int ttt_lact_swiglu_ex(const ttt_lact_shape* shape, int dtype, float eta, const 
                   options->update_mask, options->eta_tok, options->loss, options->weight_norm, options->muon,
                   (hipStream_t)options->side_stream, (hipEvent_t)options->fork_event,
                   (hipEvent_t)options->join_event};
+  a.keep = options->W_states;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = dtype == TTT_BF16 ? ttt::launch_lact<bf16>(a, s) : ttt::launch_lact<float>(a, s);
   if (e == hipErrorNotSupported) return TTT_ERR_UNSUPPORTED;

@@ -355,15 +355,19 @@ struct LactBwdWs {
   size_t fwd, keep, g, gG, cm[16], cd[2], part, gpart, total;
 };
 
+// saved: the forward call kept the states, so neither its workspace nor the
+// state slots are needed here.
 template <typename T>
-LactBwdWs lact_bwd_layout(int B, int H, int n, int dh, int m, int C) {
+LactBwdWs lact_bwd_layout(int B, int H, int n, int dh, int m, int C, bool saved = false) {
   LactBwdWs w{};
   const size_t e = sizeof(T), BH = (size_t)B * H, md = (size_t)m * dh, k = (size_t)(C > 0 ? n / C : 0);
   size_t o = 0;
-  w.fwd = o;
-  o += al256(lact_workspace_bytes<T>(B, H, n, dh, m, C));
-  w.keep = o;
-  o += al256((k + 1) * BH * 3 * md * e);
+  if (!saved) {
+    w.fwd = o;
+    o += al256(lact_workspace_bytes<T>(B, H, n, dh, m, C));
+    w.keep = o;
+    o += al256((k + 1) * BH * 3 * md * e);
+  }
   w.g = o;
   o += al256(BH * 3 * md * 4);
   w.gG = o;
@@ -425,8 +429,8 @@ hipError_t ddh(const EwArgs& a, int BH, hipStream_t s) {
 }  // namespace
 
 template <typename T>
-size_t lact_bwd_workspace_bytes(int B, int H, int n, int dh, int m, int C) {
-  return lact_bwd_layout<T>(B, H, n, dh, m, C).total;
+size_t lact_bwd_workspace_bytes(int B, int H, int n, int dh, int m, int C, bool saved) {
+  return lact_bwd_layout<T>(B, H, n, dh, m, C, saved).total;
 }
 
 template <typename T>
@@ -436,11 +440,12 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
   const int64_t md = (int64_t)m * dh;
   hipError_t e;
   if (BH == 0) return hipSuccess;
-  const LactBwdWs L = lact_bwd_layout<T>(B, H, n, dh, m, C);
+  const bool saved = a.states != nullptr;
+  const LactBwdWs L = lact_bwd_layout<T>(B, H, n, dh, m, C, saved);
   float* g = (float*)(a.ws + L.g);
   T* gG = (T*)(a.ws + L.gG);
   if ((e = launch_zero<float>(g, (int64_t)BH * 3 * md, s)) != hipSuccess) return e;
-  if (n > 0) {
+  if (n > 0 && !saved) {
     // the states: the forward's kernels on the keys alone, every chunk's state kept
     LactArgs f{};
     f.B = B;
@@ -470,7 +475,7 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     if ((e = launch_zero<float>(g, (int64_t)BH * 3 * md, s)) != hipSuccess) return e;
   }
   const int k = C > 0 ? n / C : 0;
-  const T* keep = (const T*)(a.ws + L.keep);
+  const T* keep = saved ? (const T*)a.states : (const T*)(a.ws + L.keep);
   T* cm[16];
   for (int i = 0; i < 16; ++i) cm[i] = (T*)(a.ws + L.cm[i]);
   T* A = cm[0];
@@ -650,8 +655,8 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template size_t lact_bwd_workspace_bytes<float>(int, int, int, int, int, int);
-template size_t lact_bwd_workspace_bytes<bf16>(int, int, int, int, int, int);
+template size_t lact_bwd_workspace_bytes<float>(int, int, int, int, int, int, bool);
+template size_t lact_bwd_workspace_bytes<bf16>(int, int, int, int, int, int, bool);
 template hipError_t launch_lact_backward<float>(const LactBwdArgs&, hipStream_t);
 template hipError_t launch_lact_backward<bf16>(const LactBwdArgs&, hipStream_t);
 

@@ -165,7 +165,7 @@ struct LactArgs {
   void* keep;
 };
 template <typename T>
-size_t lact_bwd_workspace_bytes(int B, int H, int n, int dh, int m, int C);
+size_t lact_bwd_workspace_bytes(int B, int H, int n, int dh, int m, int C, bool saved = false);
 // Backward of the LaCT layer (squared error, plain GD, no other variant): dq, dk, dv [B, H, n, dh] dtype and the
 // initial weights' gradients dW1, dW3 [H, m, dh], dW2 [H, dh, m] fp32, given dO; every state recomputed first.
 struct LactBwdArgs {
@@ -176,6 +176,7 @@ struct LactBwdArgs {
   float *dW1, *dW3, *dW2;
   char* ws;
   const unsigned char* update_mask;   // HOST [n / C] as in LactArgs, or null
+  const void* states;                 // the states the forward call kept (LactArgs::keep's layout), or null
 };
 template <typename T>
 hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s);

@@ -587,6 +587,16 @@ typedef struct {
   void* side_stream;
   void* fork_event;
   void* join_event;
+  /* Keeping the states for a backward pass: W_states (DEVICE, 16-byte
+   * aligned, dtype) receives, for every chunk c = 0 .. n / chunk and every
+   * (batch, head) row bh, the operand copies of the state chunk c's update
+   * starts from (slot n / chunk: the final state) -- W1 [m, dh], W3 [m, dh],
+   * W2 [dh, m] one after the other at W_states + ((c B H + bh) 3 + i) m dh,
+   * i = 0, 1, 2: (n / chunk + 1) B H 3 m dh elements.  A masked chunk's slot
+   * repeats the state it passes on.  One copy per chunk (3 B H m dh dtype
+   * elements of traffic).  ttt_lact_swiglu_backward_ex takes them and skips
+   * recomputing them.  NULL: not kept. */
+  void* W_states;
 } ttt_lact_options;
 
 /* The LaCT layer of ttt_lact_swiglu with options (above; NULL options:
@@ -631,11 +641,20 @@ int ttt_lact_swiglu_backward(const ttt_lact_shape* shape, int dtype, int order, 
                              void* dq, void* dk, void* dv, float* dW1, float* dW3, float* dW2,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes for ttt_lact_swiglu_backward_ex: with saved_states = 1 (the
+ * forward call kept its states, ttt_lact_options.W_states) the forward's
+ * workspace and the state slots are not needed; saved_states = 0 gives
+ * ttt_lact_backward_workspace_bytes.  Other values: TTT_ERR_ARG. */
+int ttt_lact_backward_workspace_bytes_ex(const ttt_lact_shape* shape, int dtype, int saved_states, size_t* bytes);
+
 /* ttt_lact_swiglu_backward with the forward call's ttt_lact_options (NULL:
  * TTT_ERR_ARG): `order` and `update_mask` (HOST, [n / chunk], as for
  * ttt_lact_swiglu_ex) are taken -- a chunk whose flag is zero was applied but
  * took no step, so the state gradient passes it unchanged and its dk and dv
- * rows are zero.  The update's variants have no backward here: eta_tok, the
+ * rows are zero.  W_states, if not NULL, holds the states the forward call
+ * kept (same options, same inputs): the call reads them instead of
+ * recomputing them, with the workspace of
+ * ttt_lact_backward_workspace_bytes_ex(..., saved_states = 1, ...).  The update's variants have no backward here: eta_tok, the
  * dot loss, weight_norm or muon give TTT_ERR_UNSUPPORTED (invalid values of
  * the flags TTT_ERR_ARG).  side_stream and its events are not read (the
  * backward runs as one chain on `stream`).  Other arguments, workspace and

@@ -420,6 +420,17 @@ def test_lact_backward_validation():
     assert ex(cw.LactOptions(0, None, None, 0, 1, 0, None, None, None)) == cw.TTT_ERR_UNSUPPORTED
     assert ex(cw.LactOptions(0, None, None, 0, 0, 1, None, None, None)) == cw.TTT_ERR_UNSUPPORTED
     assert ex(cw.LactOptions(7, None, None, 0, 0, 0, None, None, None)) == cw.TTT_ERR_ARG           # order
+    assert ex(cw.LactOptions(0, None, None, 0, 0, 0, None, None, None, ctypes.c_void_p(0x100004))) == cw.TTT_ERR_ARG
+    # kept states: the forward's workspace and the state slots drop out of the backward's
+    kept = ctypes.c_size_t(0)
+    assert lib.ttt_lact_backward_workspace_bytes_ex(ctypes.byref(good), cw.TTT_BF16, 1,
+                                                    ctypes.byref(kept)) == cw.TTT_OK
+    k, BH, md = 8192 // 4096, 4, 512 * 1024
+    assert kept.value <= nb.value - fwd.value - (k + 1) * BH * 3 * md * 2
+    assert lib.ttt_lact_backward_workspace_bytes_ex(ctypes.byref(good), cw.TTT_BF16, 0,
+                                                    ctypes.byref(kept)) == cw.TTT_OK and kept.value == nb.value
+    assert lib.ttt_lact_backward_workspace_bytes_ex(ctypes.byref(good), cw.TTT_BF16, 2,
+                                                    ctypes.byref(kept)) == cw.TTT_ERR_ARG
 
 
 def test_binding_refuses_cpu_tensors():

@@ -123,3 +123,36 @@ def test_lact_backward_with_update_mask(dtype, order):
     plain = run(cfg, x, dO)
     for a, b in zip(ones, plain):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["plain", "side", "mask", "apply_then_update"])
+def test_lact_backward_with_kept_states(dtype, variant):
+    """States kept by the forward call (ttt_lact_options.W_states; on two streams, with an update mask, or in
+    apply-then-update order) give the backward that recomputes them, bit for bit; slot 0 holds the initial weights
+    and the last slot the final state in the layer's dtype."""
+    order = "apply_then_update" if variant == "apply_then_update" else "update_then_apply"
+    cfg, x, dO = case(dtype, order, n=512, seed=85)
+    mask = [1, 0, 1, 1] if variant == "mask" else None
+    g = {k: v.cuda() for k, v in x.items()}
+    B, H, n, dh = g["q"].shape
+    m = g["W1"].shape[1]
+    k = n // cfg.chunk
+    print(f"lact kept-states case: {dtype} {variant}", flush=True)
+    Ws = torch.full((k + 1, B, H, 3, m * dh), float("nan"), dtype=g["q"].dtype, device="cuda")
+    side = cw.LactSideStream() if variant == "side" else None
+    O, W1f, W3f, W2f = cw.ttt_lact_swiglu(g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], cfg.chunk, cfg.eta, order,
+                                          update_mask=mask, side=side, W_states=Ws)
+    torch.cuda.synchronize()
+    assert not torch.isnan(Ws).any()
+    for h in range(H):
+        assert torch.equal(Ws[0, :, h, 0], g["W1"][h].reshape(-1).expand(B, -1))
+        assert torch.equal(Ws[0, :, h, 2], g["W2"][h].reshape(-1).expand(B, -1))
+    assert torch.equal(Ws[k, :, :, 0].float(), W1f.reshape(B, H, -1).to(Ws.dtype).float())
+    assert torch.equal(Ws[k, :, :, 2].float(), W2f.reshape(B, H, -1).to(Ws.dtype).float())
+    args = (g["q"], g["k"], g["v"], g["W1"], g["W3"], g["W2"], dO.cuda(), cfg.chunk, cfg.eta, order)
+    kept = cw.ttt_lact_swiglu_backward(*args, update_mask=mask, W_states=Ws)
+    again = cw.ttt_lact_swiglu_backward(*args, update_mask=mask)
+    torch.cuda.synchronize()
+    for name, a, b in zip(NAMES, kept, again):
+        assert torch.equal(a, b), name

@@ -135,6 +135,7 @@ class LactConfig:
     token_rates: bool = False     # draw per-token learning rates eta_tok ~ U(0, 1) (fp32)
     muon: bool = False            # the Muon update rule (Newton-Schulz orthogonalised gradients)
     backward: bool = False        # the layer's backward (inputs of the layer and dO)
+    kept_states: bool = False     # the backward reads the states the forward call kept
 
     @property
     def tokens(self) -> int:
@@ -157,9 +158,11 @@ class LactConfig:
         and head: the states recomputed on the keys (14), the query apply's
         backward with its recompute (16: Aq, Uq, dHq, the three weight
         gradients, dq) and the update's (36: A, U, Y, dH again, ddA, ddU, dR,
-        dHh, dk's four products, the three weight gradients)."""
+        dHh, dk's four products, the three weight gradients); 52 with the
+        states kept by the forward call."""
         if self.backward:
-            return float(self.tokens) * self.heads * 66.0 * self.head_dim * self.hidden
+            per = 52.0 if self.kept_states else 66.0
+            return float(self.tokens) * self.heads * per * self.head_dim * self.hidden
         mask = self.update_mask()
         upd = 1.0 if mask is None else sum(mask) / len(mask)
         key = 14.0 - (2.0 if self.loss == "dot" else 0.0)     # the dot loss needs no key output f(k)
@@ -222,6 +225,9 @@ WORKLOADS = {
     # the layer's backward (every input's gradient from dLoss/dO), squared error and plain GD
     "lact_bwd_bf16_256k": LactConfig("lact_bwd_bf16_256k", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
                                      backward=True),
+    # the same with the states kept by the forward call (no recompute in the backward)
+    "lact_bwd_bf16_256k_kept": LactConfig("lact_bwd_bf16_256k_kept", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
+                                          backward=True, kept_states=True),
     # the same with the update on every other chunk only (a strided block-wise mask)
     "lact_bf16_256k_strided": LactConfig("lact_bf16_256k_strided", 1, 4, 262144, 512, 1024, 4096, 1.0, seed=1004,
                                          update_every=2),
