@@ -111,9 +111,10 @@ TTT_GEMM_KERNEL(Wide) void k_bgemm(BGemmSet set) {
   using G = Wide;
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   constexpr int KR = 128 / bsz<T>();
-  int id = xcd_remap(blockIdx.x, gridDim.x);
-  // which GEMM of the set: tiles of g[0], then g[1], then g[2]
-  int which = 0;
+  // which GEMM of the set: the workgroups of g[0] first, then g[1], then g[2],
+  // in dispatch order, so that a set listing its longest tiles first starts
+  // them in the first round; the XCD-aware order then applies within each GEMM
+  int id = blockIdx.x, which = 0;
 #pragma unroll
   for (int i = 0; i < kMaxSet - 1; ++i) {
     const BGemm& gi = set.g[i];
@@ -125,6 +126,7 @@ TTT_GEMM_KERNEL(Wide) void k_bgemm(BGemmSet set) {
   }
   const BGemm& g = set.g[which];
   const int TP = (g.NP + G::BP - 1) / G::BP, TQ = (g.NQ + G::BQ - 1) / G::BQ, per = TP * TQ;
+  id = xcd_remap(id, per * g.batch * set.nsplit);
   const int bs_ = id / per;
   const int b = bs_ / set.nsplit, sp = bs_ - b * set.nsplit;
   int tp, tq;
