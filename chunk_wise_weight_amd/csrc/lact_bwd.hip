@@ -348,9 +348,10 @@ __global__ __launch_bounds__(256) void k_lact_gsum(const float* __restrict__ g, 
 // Workspace of the backward: the forward's own (for the recompute), the kept
 // states, the fp32 state gradient and its scaled operand copy, the per-chunk
 // intermediates and one fp32 [BH, C, dh] partial.
-// The state gradient's contractions over a chunk's tokens are split this many
-// ways (with 4 x 512 x 1024 states, three gradients of 32 tiles each would
-// leave most of the GPU idle); the splits' fp32 partials are then added in order.
+// The state gradient's contractions over a chunk's tokens are split at most
+// this many ways (with 4 x 512 x 1024 states, three gradients of 32 tiles each
+// would leave most of the GPU idle); the splits' fp32 partials are then added
+// in order.
 constexpr int kGradSplit = 4;
 
 struct LactBwdWs {
@@ -501,18 +502,19 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
   float* part = (float*)(a.ws + L.part);
   float* gpart = (float*)(a.ws + L.gpart);
   // the three state-gradient contractions of a phase, split over the tokens, then added into g
-  auto grad_set = [&](auto launch, BGemm g2, BGemm g1, BGemm g3) -> hipError_t {
+  // nsplit: 2 when the three have equal K (one round of 192 tiles at the workload), 4 when g2 has two K streams
+  auto grad_set = [&](auto launch, int nsplit, BGemm g2, BGemm g1, BGemm g3) -> hipError_t {
     BGemmSet set{};
     set.g[0] = g2;
     set.g[1] = g1;
     set.g[2] = g3;
     set.n = 3;
-    set.nsplit = kGradSplit;
+    set.nsplit = nsplit;
     set.split_so = (int64_t)BH * 3 * md;
     hipError_t r = launch(set);
     if (r != hipSuccess) return r;
     const int64_t n = (int64_t)BH * 3 * md;
-    k_lact_gacc<<<(unsigned)cdiv64(n / 4, 256), 256, 0, s>>>(gpart, g, n, kGradSplit);
+    k_lact_gacc<<<(unsigned)cdiv64(n / 4, 256), 256, 0, s>>>(gpart, g, n, nsplit);
     return hipGetLastError();
   };
   const int64_t S3 = 3 * md;                                 // row-group stride of states and gradients
@@ -560,7 +562,7 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
       if ((r = bgemm<T, true, false, 1, kGateQ>(gq, s)) != hipSuccess) return r;
     }
     // g2 += dO^T Hq, g1 += dAq^T Q, g3 += dUq^T Q
-    r = grad_set([&](const BGemmSet& set) { return bgemm_set<T, true, true, 1, kStoreF32>(set, s); },
+    r = grad_set([&](const BGemmSet& set) { return bgemm_set<T, true, true, 1, kStoreF32>(set, s); }, 2,
                  one(cmK(Hq), dOc, C, m, dh, gpart + 2 * md, m, S3), one(Qc, cmK(dAq), C, dh, m, gpart, dh, S3),
                  one(Qc, cmK(dUq), C, dh, m, gpart + md, dh, S3));
     if (r != hipSuccess) return r;
@@ -632,7 +634,7 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     BGemm g1 = one(Kc, cmK(dAf), C, dh, m, gpart, dh, S3), g3 = one(Kc, cmK(dUf), C, dh, m, gpart + md, dh, S3);
     g1 = two(g1, g1.P[0], g1.Q[0], 0);
     g3 = two(g3, g3.P[0], g3.Q[0], 0);
-    return grad_set([&](const BGemmSet& set) { return bgemm_set<T, true, true, 2, kStoreF32>(set, s); },
+    return grad_set([&](const BGemmSet& set) { return bgemm_set<T, true, true, 2, kStoreF32>(set, s); }, kGradSplit,
                     two(one(cmK(ddH), cdK(R), C, m, dh, gpart + 2 * md, m, S3), cmK(Hh), cdK(dR), C), g1, g3);
   };
 
