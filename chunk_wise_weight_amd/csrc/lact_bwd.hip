@@ -64,16 +64,14 @@ struct BOp {
 //             x U) silu'(A), eo1 = dU_f = ddA dH silu'(A) + x S
 //             (in: A, U, dH, ddA, ddU)
 //   kStoreNeg: out = x and eo0 = -x (eo0 rows ldo apart, batch stride eo_so)
-enum { kStoreT = 0, kStoreF32 = 1, kAccF32 = 2, kAddF32ToT = 3, kGateKey = 4, kGateQ = 5, kGateF = 6, kStoreNeg = 7 };
+enum { kStoreT = 0, kStoreF32 = 1, kAccF32 = 2, kGateKey = 4, kGateQ = 5, kGateF = 6, kStoreNeg = 7 };
 
 struct BGemm {
-  BOp P[2], Q[2];
-  int K[2];          // contraction length of each stream (K[1] = 0: one stream)
+  BOp P[4], Q[4];
+  int K[4];          // contraction length of each stream (0: the stream is empty)
   int NP, NQ, batch;
   void* out;         // out[b][q][p] at out + b so + q ldo + p
   int64_t ldo, so;
-  const float* add;  // kAddF32ToT: out = alpha acc + add, add[b][q][p] at add + b add_so + q ldo + p
-  int64_t add_so;
   float alpha;
   const void* in[5];  // the gate modes' inputs (dtype, layout of out)
   void* eo[2];        // the gate modes' and kStoreNeg's extra outputs (dtype)
@@ -133,32 +131,26 @@ TTT_GEMM_KERNEL(Wide) void k_bgemm(BGemmSet set) {
   grouped_tile(id - bs_ * per, TP, TQ, 4, tp, tq);
   const int p0 = tp * G::BP, q0 = tq * G::BQ;
   // this split's K range, whole K steps (every stream the same)
-  const int kmax = max(g.K[0], g.K[1]);
+  int kmax = 0;
+#pragma unroll
+  for (int st = 0; st < NS; ++st) kmax = max(kmax, g.K[st]);
   const int ks = ((kmax + set.nsplit - 1) / set.nsplit + KR - 1) / KR * KR;
   const int k0 = sp * ks;
-  const int K0 = max(0, min(ks, g.K[0] - k0)), K1 = max(0, min(ks, g.K[1] - k0));
   typename G::Frag acc[G::NPB][G::NQB];
   zero_acc<G>(acc);
-  if constexpr (NS == 1) {
+  // the streams one after the other on one accumulator, each with its own
+  // operand state, so that only one stream's DMA offsets are live at a time
+  // (two at once spill); each K loop ends on a barrier, so the next may refill
+  // the stages at once
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    const int Ks = max(0, min(ks, g.K[st] - k0));
+    if (Ks <= 0) continue;
     OpOf<T, PMN, G::BP> op;
     OpOf<T, QMN, G::BQ> oq;
-    init_op<T, PMN, G::BP>(op, g.P[0], b, p0, g.NP, K0, k0);
-    init_op<T, QMN, G::BQ>(oq, g.Q[0], b, q0, g.NQ, K0, k0);
-    mainloop<T, G>(op, oq, (K0 + KR - 1) / KR, acc, smem, NoHook{});
-  } else {
-    // the two streams one after the other, each with its own operand state, so
-    // that only one stream's DMA offsets are live at a time (both at once spill);
-    // each K loop ends on a barrier, so the second may refill the stages at once
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int Ks = st == 0 ? K0 : K1;
-      if (Ks <= 0) continue;
-      OpOf<T, PMN, G::BP> op;
-      OpOf<T, QMN, G::BQ> oq;
-      init_op<T, PMN, G::BP>(op, g.P[st], b, p0, g.NP, Ks, k0);
-      init_op<T, QMN, G::BQ>(oq, g.Q[st], b, q0, g.NQ, Ks, k0);
-      mainloop<T, G>(op, oq, (Ks + KR - 1) / KR, acc, smem, NoHook{});
-    }
+    init_op<T, PMN, G::BP>(op, g.P[st], b, p0, g.NP, Ks, k0);
+    init_op<T, QMN, G::BQ>(oq, g.Q[st], b, q0, g.NQ, Ks, k0);
+    mainloop<T, G>(op, oq, (Ks + KR - 1) / KR, acc, smem, NoHook{});
   }
 
   // out[q][p]: staged by rows q (p contiguous), in passes when a whole tile
@@ -169,7 +161,6 @@ TTT_GEMM_KERNEL(Wide) void k_bgemm(BGemmSet set) {
   const Staged<float, G::BP> st{smem};
   const int qn = min(G::BQ, g.NQ - q0), pn = min(G::BP, g.NP - p0);
   TO* out = (TO*)g.out + (int64_t)b * g.so + (int64_t)sp * set.split_so;
-  const float* add = g.add != nullptr ? g.add + (int64_t)b * g.add_so : nullptr;
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
 #pragma unroll
@@ -248,7 +239,6 @@ TTT_GEMM_KERNEL(Wide) void k_bgemm(BGemmSet set) {
         const int64_t o = (int64_t)(q0 + ps * RPP + r) * g.ldo + p0 + c;
         f32x4 v = *reinterpret_cast<const f32x4*>(smem + st.off(r, c));
         if constexpr (MODE == kAccF32) v += load4(out + o);
-        if constexpr (MODE == kAddF32ToT) v += load4(add + o);
         store4(out + o, v[0], v[1], v[2], v[3]);
         if constexpr (MODE == kStoreNeg)
           store4((T*)g.eo[0] + (int64_t)b * g.eo_so + o, -v[0], -v[1], -v[2], -v[3]);
@@ -355,7 +345,7 @@ __global__ __launch_bounds__(256) void k_lact_gsum(const float* __restrict__ g, 
 constexpr int kGradSplit = 4;
 
 struct LactBwdWs {
-  size_t fwd, keep, g, gG, cm[16], cd[2], part, gpart, total;
+  size_t fwd, keep, g, gG, cm[16], cd[2], gpart, total;
 };
 
 // saved: the forward call kept the states, so neither its workspace nor the
@@ -383,8 +373,6 @@ LactBwdWs lact_bwd_layout(int B, int H, int n, int dh, int m, int C, bool saved 
     w.cd[i] = o;
     o += al256(BH * (size_t)C * dh * e);
   }
-  w.part = o;
-  o += al256(BH * (size_t)C * dh * 4);
   w.gpart = o;
   o += al256((size_t)kGradSplit * BH * 3 * md * 4);
   w.total = o;
@@ -499,7 +487,6 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
   T* dUq = cm[15];
   T* R = (T*)(a.ws + L.cd[0]);
   T* dR = (T*)(a.ws + L.cd[1]);
-  float* part = (float*)(a.ws + L.part);
   float* gpart = (float*)(a.ws + L.gpart);
   // the three state-gradient contractions of a phase, split over the tokens, then added into g
   // nsplit: 2 when the three have equal K (one round of 192 tiles at the workload), 4 when g2 has two K streams
@@ -522,8 +509,7 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
   // a [BH, C, x] intermediate as a K-major (token rows) or MN-major (tokens as K) operand
   auto cmK = [&](const T* p) { return BOp{p, m, Scm}; };
   auto cdK = [&](const T* p) { return BOp{p, dh, Scd}; };
-  auto one = [&](BOp P, BOp Q, int K, int NP, int NQ, void* out, int64_t ldo, int64_t so, float alpha = 1.0f,
-                 const float* add = nullptr) {
+  auto one = [&](BOp P, BOp Q, int K, int NP, int NQ, void* out, int64_t ldo, int64_t so, float alpha = 1.0f) {
     BGemm gm{};
     gm.P[0] = P;
     gm.Q[0] = Q;
@@ -535,7 +521,6 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     gm.ldo = ldo;
     gm.so = so;
     gm.alpha = alpha;
-    gm.add = add;
     return gm;
   };
   auto two = [&](BGemm gm, BOp P2, BOp Q2, int K2) {
@@ -544,6 +529,24 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     gm.K[1] = K2;
     return gm;
   };
+  auto four = [&](BGemm gm, BOp P3, BOp Q3, int K3, BOp P4, BOp Q4, int K4) {
+    gm.P[2] = P3;
+    gm.Q[2] = Q3;
+    gm.K[2] = K3;
+    gm.P[3] = P4;
+    gm.Q[3] = Q4;
+    gm.K[3] = K4;
+    return gm;
+  };
+  // dq of a chunk waits for the next dk launch, whose 128 tiles it fills up to one round (its dAq, dUq stay intact
+  // until the next query pass, which launches a dq still pending on its own first)
+  BGemm pending_dq{};
+  bool dq_pending = false;
+  auto flush_dq = [&]() -> hipError_t {
+    if (!dq_pending) return hipSuccess;
+    dq_pending = false;
+    return bgemm<T, true, false, 4, kStoreT>(pending_dq, s);
+  };
 
   // queries of a chunk applied with the state W (slot pointer, rows 3 m dh apart)
   auto query_backward = [&](const T* W, int c) -> hipError_t {
@@ -551,6 +554,7 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     const BOp Qc{(const T*)a.q + (int64_t)c * C * dh, dh, Sn};
     const BOp dOc{(const T*)a.dO + (int64_t)c * C * dh, dh, Sn};
     hipError_t r;
+    if ((r = flush_dq()) != hipSuccess) return r;
     // Aq, Uq and Hq by the forward's gate kernel; dHq = dO W2 with dAq, dUq formed in its epilogue
     if ((r = launch_lact_gate_pass<T>((const T*)a.q, W, S3, Aq, Uq, Hq, BH, n, dh, m, C, c, s)) != hipSuccess) return r;
     {
@@ -566,10 +570,11 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
                  one(cmK(Hq), dOc, C, m, dh, gpart + 2 * md, m, S3), one(Qc, cmK(dAq), C, dh, m, gpart, dh, S3),
                  one(Qc, cmK(dUq), C, dh, m, gpart + md, dh, S3));
     if (r != hipSuccess) return r;
-    // dq = dAq W1 + dUq W3
-    return bgemm<T, true, false, 2, kStoreT>(
-        two(one({W1, dh, S3}, cmK(dAq), m, dh, C, (T*)a.dq + (int64_t)c * C * dh, dh, Sn), {W3, dh, S3}, cmK(dUq), m),
-        s);
+    // dq = dAq W1 + dUq W3, launched with the next dk
+    pending_dq = two(one({W1, dh, S3}, cmK(dAq), m, dh, C, (T*)a.dq + (int64_t)c * C * dh, dh, Sn), {W3, dh, S3},
+                     cmK(dUq), m);
+    dq_pending = true;
+    return hipSuccess;
   };
 
   // the update of chunk c from the state W, upstream gG = -eta g
@@ -617,17 +622,21 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
       gf.eo[1] = dUf;
       if ((r = bgemm<T, true, false, 2, kGateF>(gf, s)) != hipSuccess) return r;
     }
-    // dk = (dA gG1 + dU gG3) + (dA_f W1 + dU_f W3), the first pair in fp32
-    if ((r = bgemm<T, true, false, 2, kStoreF32>(
-             two(one({gG1, dh, S3}, cmK(dA), m, dh, C, part, dh, Scd), {gG3, dh, S3}, cmK(dU), m), s)) != hipSuccess)
-      return r;
+    // dk = dA gG1 + dU gG3 + dA_f W1 + dU_f W3: four K streams on one accumulator, rounded once into the
+    // chunk's rows of dk (row group stride n dh); a pending dq (two streams) joins the launch
     {
-      // the second pair, written as the chunk's rows of dk (row group stride n dh) with the first pair added
-      BGemm gk = two(one({W1, dh, S3}, cmK(dAf), m, dh, C, (T*)a.dk + (int64_t)c * C * dh, dh, Sn),
-                     {W3, dh, S3}, cmK(dUf), m);
-      gk.add = part;
-      gk.add_so = Scd;
-      if ((r = bgemm<T, true, false, 2, kAddF32ToT>(gk, s)) != hipSuccess) return r;
+      BGemmSet set{};
+      set.g[0] = four(two(one({gG1, dh, S3}, cmK(dA), m, dh, C, (T*)a.dk + (int64_t)c * C * dh, dh, Sn), {gG3, dh, S3},
+                          cmK(dU), m),
+                      {W1, dh, S3}, cmK(dAf), m, {W3, dh, S3}, cmK(dUf), m);
+      set.n = 1;
+      set.nsplit = 1;
+      if (dq_pending) {
+        set.g[1] = pending_dq;
+        set.n = 2;
+        dq_pending = false;
+      }
+      if ((r = bgemm_set<T, true, false, 4, kStoreT>(set, s)) != hipSuccess) return r;
     }
     // g2 += R^T ddH + dR^T Hh, g1 += dA_f^T k, g3 += dU_f^T k (the last two as one-stream members of a
     // two-stream set: their second stream is empty)
@@ -655,6 +664,7 @@ hipError_t launch_lact_backward(const LactBwdArgs& a, hipStream_t s) {
     }
     if (a.order != 0 && (e = query_backward(Wc, c)) != hipSuccess) return e;
   }
+  if ((e = flush_dq()) != hipSuccess) return e;
   k_lact_gsum<<<dim3((unsigned)cdiv64(md / 4, 256), (unsigned)(3 * H)), 256, 0, s>>>(g, a.dW1, a.dW3, a.dW2, B, H, md);
   return hipGetLastError();
 }
