@@ -152,9 +152,12 @@ def grad_mse(W, Zc, Vc):
 _GRADS = {"dot": grad_dot, "mse": grad_mse}
 
 
-def chunk_apply_update(Z, Vhat, W0, chunk, eta, mode):
+def chunk_apply_update(Z, Vhat, W0, chunk, eta, mode, update_first=False):
     """The sequential definition (Method §1): for each chunk in order, apply the
     current state (eq. (3)), then take one gradient step on it (eq. (4)).
+    `update_first` takes the step first and applies the updated state (the
+    update-then-apply order of the LaCT review's section on the order of the
+    two operations); W_final is the same in both orders.
 
     Z [n, f], Vhat [n, d], W0 [d, f].  A last chunk shorter than `chunk` is
     allowed here (it is simply the remaining tokens).
@@ -167,8 +170,11 @@ def chunk_apply_update(Z, Vhat, W0, chunk, eta, mode):
     O = np.empty((n, W.shape[0]))
     for start in range(0, n, chunk):
         rows = slice(start, min(start + chunk, n))
-        O[rows] = Z[rows] @ W.T                       # apply: state before this chunk
+        if not update_first:
+            O[rows] = Z[rows] @ W.T                   # apply: state before this chunk
         W = W - eta * grad(W, Z[rows], Vhat[rows])     # update: gradient at that state
+        if update_first:
+            O[rows] = Z[rows] @ W.T                   # apply: the state after this chunk's step
     return O, W
 
 
@@ -316,7 +322,7 @@ def chunk_prefix_form(Z, Vhat, W0, chunk, eta):
 
 def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
                   mode, max_chunks=None, x0_halo=None, doc_starts=None, conv_forward=False, W_init=None,
-                  update_mask=None):
+                  update_mask=None, update_first=False):
     """The whole In-Place TTT layer, one document per batch row.
 
     H, X0 [B, n, d]; W_gate, W_up [f, d]; W_down0 [d, f]; W_target [d, d];
@@ -342,6 +348,10 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
     step on the flagged chunks only; every chunk is applied (the strided
     update of the LaCT review's section on the order of the apply and update
     operations, read onto this layer).
+
+    `update_first` takes each chunk's step before its apply (as in
+    chunk_apply_update): chunk c's outputs then see its own targets, so the
+    layer is no longer causal inside a chunk -- for non-causal uses.
 
     `max_chunks` stops after that many chunks (O then covers only those rows
     and W_final is the state after them) -- used to time a bounded sample.
@@ -381,9 +391,12 @@ def inplace_layer(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk, eta,
                 Y = causal_depthwise_conv1d(Xfull[lo: e + off], conv_w)[-(e - s):]
             Vc = Y @ W_target
             Zc = gated_intermediate(H[b, s:e], W_gate, W_up)
-            O[b, s:e] = Zc @ W.T
+            if not update_first:
+                O[b, s:e] = Zc @ W.T
             if update_mask is None or update_mask[b][c]:
                 W = W - eta * grad(W, Zc, Vc)
+            if update_first:
+                O[b, s:e] = Zc @ W.T
         W_final[b] = W
     return O, W_final
 

@@ -1005,3 +1005,48 @@ def test_resumed_core_backward_matches_autograd(mode):
     for a, b in zip(r[:3], back(Z, V, W0, C, eta, dO, doc_starts=flagged)):
         np.testing.assert_array_equal(a, b)
     assert not r[3].any()
+
+
+# ---------------------------------------------------------------- update-then-apply order
+
+def test_update_first_dot_closed_form():
+    """Dot objective, update first: O_c = Z_c (W_c + eta V^_c^T Z_c)^T = the apply-then-update output plus
+    eta (Z_c Z_c^T) V^_c, the chunk's own targets through its token Gram matrix; W_final is the same in both
+    orders."""
+    rng = _rng(90)
+    n, C, d, f, eta = 13, 4, 3, 5, 0.3
+    Z, V, W0 = rng.standard_normal((n, f)), rng.standard_normal((n, d)), rng.standard_normal((d, f))
+    Oa, Wa = orc.chunk_apply_update(Z, V, W0, C, eta, "dot")
+    Ou, Wu = orc.chunk_apply_update(Z, V, W0, C, eta, "dot", update_first=True)
+    want = Oa.copy()
+    for s in range(0, n, C):
+        Zc, Vc = Z[s:s + C], V[s:s + C]
+        want[s:s + C] += eta * (Zc @ Zc.T) @ Vc
+    np.testing.assert_allclose(Ou, want, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(Wu, Wa)
+
+
+@pytest.mark.parametrize("mode", ["dot", "mse"])
+def test_update_first_layer_equals_truncated_final_states(mode):
+    """The layer with update_first: chunk c's outputs are Z_c times the W_final of the apply-then-update layer
+    stopped after chunk c (max_chunks = c + 1), for every row of a packed, masked, resumed batch; the final states
+    equal the apply-then-update layer's."""
+    rng = _rng(91)
+    B, n, C, d, f, K, eta = 2, 12, 4, 3, 4, 3, 0.4
+    shapes = ((B, n, d), (B, n, d), (f, d), (f, d), (d, f), (d, d), (d, K))
+    args = [rng.standard_normal(sh) * 0.7 for sh in shapes]
+    docs = [[0, 1, 0], [0, 0, 0]]
+    mask = [[1, 1, 0], [0, 1, 1]]
+    Wi = rng.standard_normal((B, d, f)) * 0.5
+    halo = rng.standard_normal((B, K - 1, d))
+    kw = dict(doc_starts=docs, update_mask=mask, W_init=Wi, x0_halo=halo)
+    Ou, Wu = orc.inplace_layer(*args, C, eta, mode, update_first=True, **kw)
+    Oa, Wa = orc.inplace_layer(*args, C, eta, mode, **kw)
+    np.testing.assert_array_equal(Wu, Wa)
+    for c in range(n // C):
+        _, Wc = orc.inplace_layer(*args, C, eta, mode, max_chunks=c + 1, **kw)
+        for b in range(B):
+            Zc = orc.gated_intermediate(args[0][b, c * C:(c + 1) * C], args[2], args[3])
+            np.testing.assert_allclose(Ou[b, c * C:(c + 1) * C], Zc @ Wc[b].T, rtol=1e-12, atol=1e-12)
+    # a masked chunk takes no step, so both orders apply it with the same state
+    np.testing.assert_array_equal(Ou[0, 8:12], Oa[0, 8:12])
