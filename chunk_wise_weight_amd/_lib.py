@@ -30,7 +30,8 @@ class InplaceShape(ctypes.Structure):
 
 class LayerOptions(ctypes.Structure):
     _fields_ = [("doc_starts", ctypes.c_void_p), ("conv_forward", ctypes.c_int), ("W_init", ctypes.c_void_p),
-                ("x0_halo", ctypes.c_void_p), ("W_states", ctypes.c_void_p), ("update_mask", ctypes.c_void_p)]
+                ("x0_halo", ctypes.c_void_p), ("W_states", ctypes.c_void_p), ("update_mask", ctypes.c_void_p),
+                ("update_first", ctypes.c_int)]
 
 
 class LactOptions(ctypes.Structure):
@@ -228,7 +229,7 @@ def _workspace(nbytes: int, device, workspace):
 
 def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk: int, eta: float, mode="dot",
                            O=None, W_final=None, workspace=None, doc_starts=None, conv_forward=False, W_init=None,
-                           x0_halo=None, W_states=None, update_mask=None):
+                           x0_halo=None, W_states=None, update_mask=None, update_first=False):
     """The whole In-Place layer.  Returns (O [B, n, d], W_final [B, d, f] fp32).
 
     Options (ttt_chunk_apply_update_ex): doc_starts, a uint8 (or bool) device tensor [B, seq_len // chunk] whose
@@ -236,7 +237,8 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
     in-chunk convolution for the target; W_init [B, d, f] fp32 and x0_halo [B, K-1, d] to resume rows from an
     earlier call (its W_final and its last K-1 rows of X0); W_states [B, seq_len // chunk, d, f] (dtype) to keep
     the per-chunk states of the dot objective for ttt_core_backward; update_mask, a uint8 (or bool) device tensor
-    [B, seq_len // chunk] whose zero entries mark chunks that are applied without updating the state."""
+    [B, seq_len // chunk] whose zero entries mark chunks that are applied without updating the state;
+    update_first, each chunk's step taken before its apply (modes "dot_scan" and "mse")."""
     B, n, d = H.shape
     f = W_gate.shape[0]
     K = conv_w.shape[1]
@@ -260,7 +262,7 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
         _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
     update_mask = _flags(update_mask, "update_mask", (B, n // chunk if chunk > 0 else 0), dev)
     if doc_starts is None and not conv_forward and W_init is None and x0_halo is None and W_states is None and \
-            update_mask is None:
+            update_mask is None and not update_first:
         _check(lib().ttt_chunk_apply_update(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
                                             _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
                                             _ptr(conv_w), _ptr(O), _ptr(W_final), _ptr(ws), nbytes, _stream(dev)),
@@ -272,7 +274,7 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
         _need(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), torch.uint8, dev)
     ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else None
     opts = LayerOptions(ptr(doc_starts), 1 if conv_forward else 0, ptr(W_init), ptr(x0_halo), ptr(W_states),
-                        ptr(update_mask))
+                        ptr(update_mask), 1 if update_first else 0)
     _check(lib().ttt_chunk_apply_update_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(H),
                                            _ptr(X0), _ptr(W_gate), _ptr(W_up), _ptr(W_down0), _ptr(W_target),
                                            _ptr(conv_w), ctypes.byref(opts), _ptr(O), _ptr(W_final), _ptr(ws),
@@ -305,10 +307,11 @@ def ttt_chunk_apply_update_noalloc(H, X0, W_gate, W_up, W_down0, W_target, conv_
 
 
 def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", O=None, W_final=None,
-                          workspace=None, W_states=None, update_mask=None, doc_starts=None, W_init=None):
+                          workspace=None, W_states=None, update_mask=None, doc_starts=None, W_init=None,
+                          update_first=False):
     """The chunk loop given Z [B, n, f] and Vhat [B, n, d].  Returns (O, W_final).  W_states [B, n // chunk, d, f]
-    (dtype), if given, receives the per-chunk states; update_mask and doc_starts [B, n // chunk] and W_init
-    [B, d, f] fp32 as for the layer (all through ttt_core_apply_update_ex)."""
+    (dtype), if given, receives the per-chunk states; update_mask and doc_starts [B, n // chunk], W_init
+    [B, d, f] fp32 and update_first as for the layer (all through ttt_core_apply_update_ex)."""
     B, n, f = Z.shape
     d = Vhat.shape[2]
     dt, dev = Z.dtype, Z.device
@@ -324,12 +327,14 @@ def ttt_core_apply_update(Z, Vhat, W_down0, chunk: int, eta: float, mode="dot", 
     ws = _workspace(nbytes, dev, workspace)
     update_mask = _flags(update_mask, "update_mask", (B, n // chunk if chunk > 0 else 0), dev)
     doc_starts = _flags(doc_starts, "doc_starts", (B, n // chunk if chunk > 0 else 0), dev)
-    if W_states is not None or update_mask is not None or doc_starts is not None or W_init is not None:
+    if W_states is not None or update_mask is not None or doc_starts is not None or W_init is not None or \
+            update_first:
         if W_states is not None:
             _need(W_states, "W_states", (B, n // chunk, d, f), dt, dev)
         if W_init is not None:
             _need(W_init, "W_init", (B, d, f), torch.float32, dev)
-        opts = LayerOptions(_vp(doc_starts), 0, _vp(W_init), None, _vp(W_states), _vp(update_mask))
+        opts = LayerOptions(_vp(doc_starts), 0, _vp(W_init), None, _vp(W_states), _vp(update_mask),
+                            1 if update_first else 0)
         _check(lib().ttt_core_apply_update_ex(ctypes.byref(shape), _dt(dt), _mode(mode), float(eta), _ptr(Z),
                                               _ptr(Vhat), _ptr(W_down0), ctypes.byref(opts), _ptr(O), _ptr(W_final),
                                               _ptr(ws), nbytes, _stream(dev)),

@@ -39,6 +39,7 @@ struct Plan {
   const void* halo;     // resumed rows: X0 rows before the first token [B, K-1, d] (device) or null
   void* states;         // dot objective: where the per-chunk states go [B, k, d, f] (device), or null: workspace
   const uint8_t* umask; // update mask [B, k] (device) or null: every chunk updates
+  bool update_first;    // each chunk's step before its apply
 };
 
 int check_inplace_shape(const ttt_inplace_shape* s, int dtype) {
@@ -70,6 +71,7 @@ int make_plan(const ttt_inplace_shape* s, int dtype, int mode, bool producers, P
   p->halo = nullptr;
   p->states = nullptr;
   p->umask = nullptr;
+  p->update_first = false;
   p->mode = mode;
   p->B = s->batch;
   p->n = s->seq_len;
@@ -162,8 +164,11 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
       if (p.states != nullptr)      // the state this chunk's apply reads, kept for a backward pass
         st = dev(ttt::launch_keep_state<T>(W0, Wcur, (T*)p.states, p.docs, p.Winit != nullptr, B, k, c, df, s));
       if (st == TTT_OK)
-        st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Wf, Wsh, O, Rt, p.docs, p.Winit != nullptr, B, n, d, f, C,
-                                          c, eta, s, p.umask));
+        st = dev(ttt::launch_mse_chunk<T>(Zt, Vt, W0, Wcur, Wf, Wsh, p.update_first ? nullptr : O, Rt, p.docs,
+                                          p.Winit != nullptr, B, n, d, f, C, c, eta, s, p.umask));
+      // update first: the chunk applied again with the state its step left
+      if (st == TTT_OK && p.update_first)
+        st = dev(ttt::launch_mse_apply_state<T>(Zt, Wcur, O, B, n, d, f, C, c, s));
       if (st != TTT_OK) return st;
     }
     return TTT_OK;
@@ -176,7 +181,8 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
   } else {
     float* dW = (float*)(ws + p.off_dW);
     st = dev(ttt::launch_chunk_delta<T>(Zt, Vt, dW, B, n, d, f, C, s));
-    if (st == TTT_OK) st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, df, eta, p.docs, p.Winit, s));
+    if (st == TTT_OK)
+      st = dev(ttt::launch_chunk_scan<T>(dW, W0, Wc, Wf, B, k, df, eta, p.docs, p.Winit, s, p.update_first));
   }
   if (st != TTT_OK) return st;
   return dev(ttt::launch_apply<T>(Zt, Wc, (int64_t)k * df, df, O, B, n, d, f, C, 1.0f, s));
@@ -206,6 +212,9 @@ int run_producers(const Plan& p, const void* H, const void* X0, const void* Wg, 
 int apply_options(Plan& p, int mode, const ttt_layer_options* o, bool producers) {
   if (o == nullptr) return TTT_OK;
   if (producers && o->conv_forward != 0 && o->conv_forward != 1) return TTT_ERR_ARG;
+  if (o->update_first != 0 && o->update_first != 1) return TTT_ERR_ARG;
+  if (o->update_first == 1 && (mode == TTT_MODE_DOT || o->W_states != nullptr)) return TTT_ERR_UNSUPPORTED;
+  p.update_first = o->update_first == 1;
   if ((o->W_init != nullptr && !ok_ptr(o->W_init)) || (producers && o->x0_halo != nullptr && !ok_ptr(o->x0_halo)) ||
       (o->W_states != nullptr && !ok_ptr(o->W_states)))
     return TTT_ERR_ARG;

@@ -626,11 +626,13 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_delta(const T* __restrict__ Zt, const T* __re
 
 // Exclusive prefix scan over chunks (Method §3, steps 2-3), four elements per
 // thread: Wc[b, c] = W0 + eta * sum_{j<c} dW[b, j]; W_final = W0 + eta * sum_all.
+// Inclusive (the update-then-apply order): Wc[b, c] = W0 + eta * sum_{j<=c}
+// dW[b, j], the state after chunk c's own step.
 template <typename T>
 __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW, const T* __restrict__ W0,
                                                     T* __restrict__ Wc, float* __restrict__ Wf, int k, int64_t df,
                                                     float eta, const uint8_t* __restrict__ docs,
-                                                    const float* __restrict__ Winit) {
+                                                    const float* __restrict__ Winit, bool inclusive) {
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   const int b = blockIdx.y;
   if (e >= df) return;
@@ -645,9 +647,10 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW
       s = (f32x4){0.f, 0.f, 0.f, 0.f};
       base = w0;
     }
+    if (inclusive) s += load4(src + (int64_t)c * df);
     store4(dst + (int64_t)c * df, fmaf(eta, s[0], base[0]), fmaf(eta, s[1], base[1]), fmaf(eta, s[2], base[2]),
            fmaf(eta, s[3], base[3]));
-    s += load4(src + (int64_t)c * df);
+    if (!inclusive) s += load4(src + (int64_t)c * df);
   }
   store4(Wf + (int64_t)b * df + e, fmaf(eta, s[0], base[0]), fmaf(eta, s[1], base[1]), fmaf(eta, s[2], base[2]),
          fmaf(eta, s[3], base[3]));
@@ -1151,8 +1154,9 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
   // Rt [b, channel, token] = rscale (O - V^) in fp32: the accumulators are staged as
   // fp32 [channel][token] rows (in passes over channels); each thread then
   // takes 8 consecutive tokens of one channel, reads V^ from Vt in one or two
-  // 16-byte pieces, subtracts and writes the same span of Rt.
-  {
+  // 16-byte pieces, subtracts and writes the same span of Rt.  Skipped when
+  // Rt is null (an apply with no residual).
+  if (Rt != nullptr) {
     constexpr int RPP = G::Smem / (G::BQ * 4);        // channel rows per pass
     constexpr int PASSES = G::BP / RPP;
     constexpr int SPANS = G::BQ / 8;                  // 8-token spans per row
@@ -1339,10 +1343,10 @@ hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n,
 
 template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
-                             const uint8_t* docs, const float* Winit, hipStream_t s) {
+                             const uint8_t* docs, const float* Winit, hipStream_t s, bool inclusive) {
   if (B == 0) return hipSuccess;
   k_chunk_scan<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(dW, W0, Wc, Wf, k, df, eta, docs,
-                                                                                 Winit);
+                                                                                 Winit, inclusive);
   return hipGetLastError();
 }
 
@@ -1493,6 +1497,17 @@ hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur
   return hipGetLastError();
 }
 
+// The update-then-apply order's apply: O_c = Z_c W^T with the state chunk c's
+// step left (Wcur, this row's copy), no residual.
+template <typename T>
+hipError_t launch_mse_apply_state(const T* Zt, const T* Wcur, T* O, int B, int n, int d, int f, int Cs, int c,
+                                  hipStream_t s) {
+  const unsigned ga = tiles_u(cdiv(Cs, kWB) * cdiv(d, kWB) * B);
+  k_mse_apply<T, false, false><<<ga, Wide::NT, 0, s>>>(Zt, Wcur, Wcur, O, nullptr, nullptr, nullptr, n, d, f, Cs, c,
+                                                       0.f, true, nullptr, 0.f, 1.f, (int64_t)d * f);
+  return hipGetLastError();
+}
+
 // The states a resumed MSE scan starts from: Wf[b] = Winit[b] (fp32) and, for
 // a dtype operand, Wsh[b] its rounded copy for the first apply.
 template <typename T>
@@ -1524,7 +1539,7 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
                                              const uint8_t*, int);                                                \
   template hipError_t launch_chunk_delta<T>(const T*, const T*, float*, int, int, int, int, int, hipStream_t);   \
   template hipError_t launch_chunk_scan<T>(const float*, const T*, T*, float*, int, int, int64_t, float,         \
-                                           const uint8_t*, const float*, hipStream_t);                            \
+                                           const uint8_t*, const float*, hipStream_t, bool);                      \
   template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, T*, float*, int,      \
                                                   int, int, int, int, int, const uint8_t*, const float*,          \
                                                   hipStream_t, int);                                              \
@@ -1549,6 +1564,8 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
   template hipError_t launch_conv_bwd<T>(const T*, const T*, const T*, T*, float*, int64_t, int, int, int,        \
                                          hipStream_t, const uint8_t*, int, bool, const T*, T*);                   \
   template hipError_t launch_zero<T>(T*, int64_t, hipStream_t);                                                   \
+  template hipError_t launch_mse_apply_state<T>(const T*, const T*, T*, int, int, int, int, int, int,          \
+                                                hipStream_t);                                                     \
   template hipError_t launch_mse_chunk<T>(const T*, const T*, const T*, const T*, float*, T*, T*, T*,             \
                                           const uint8_t*, bool, int, int, int, int, int, int, float, hipStream_t,  \
                                           const uint8_t*, bool);                                                  \

@@ -26,7 +26,7 @@ template <typename T>
 hipError_t launch_chunk_delta(const T* Zt, const T* Vt, float* dW, int B, int n, int d, int f, int C, hipStream_t s);
 template <typename T>
 hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int B, int k, int64_t df, float eta,
-                             const uint8_t* docs, const float* Winit, hipStream_t s);
+                             const uint8_t* docs, const float* Winit, hipStream_t s, bool inclusive = false);
 // Operand layouts of the fused update-scan: the token-contiguous copies Zt
 // [B, f, n] and Vt [B, d, n]; Z [B, n, f] and V [B, n, d] as they are; the
 // latter with the chunks scanned last to first.
@@ -137,6 +137,9 @@ __host__ __device__ inline int64_t conv_bwd_partials(int64_t rows) {
 // p [n] = 0 (n % 4 == 0).
 template <typename T>
 hipError_t launch_zero(T* p, int64_t n, hipStream_t s);
+template <typename T>
+hipError_t launch_mse_apply_state(const T* Zt, const T* Wcur, T* O, int B, int n, int d, int f, int Cs, int c,
+                                  hipStream_t s);
 template <typename T>
 hipError_t launch_mse_chunk(const T* Zt, const T* Vt, const T* W0, const T* Wcur, float* Ws, T* Wsh, T* O,
                             T* Rt, const uint8_t* docs, bool cont, int B, int n, int d, int f, int C, int c,

@@ -207,6 +207,19 @@ typedef struct {
    * next chunk sees the same state.  A document start still resets to
    * W_down0.  NULL: every chunk updates. */
   const unsigned char* update_mask;
+  /* 0: apply then update (Method §3: chunk c is applied with the state before
+   * its own step).  1: update then apply (the other order of the LaCT
+   * review's section on the order of the two operations): chunk c's step is
+   * taken first and the chunk is applied with the state after it, so its
+   * outputs see its own targets -- the layer is then not causal inside a
+   * chunk, for non-causal uses.  W_final is the same in both orders.  With
+   * the dot objective this runs the materialised plan: mode TTT_MODE_DOT_SCAN
+   * (its scan writes the states after each chunk), with that mode's
+   * workspace; TTT_MODE_DOT gives TTT_ERR_UNSUPPORTED.  The MSE objective
+   * applies each chunk a second time, after its step (one more apply's work).
+   * Not with W_states (TTT_ERR_UNSUPPORTED): the backward passes take the
+   * apply-then-update order.  Other values: TTT_ERR_ARG. */
+  int update_first;
 } ttt_layer_options;
 
 /* The layer of ttt_chunk_apply_update with options (above); same arguments,

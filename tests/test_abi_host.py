@@ -370,6 +370,28 @@ def test_forward_rejects_misaligned_kept_states():
                                         _fake(), _fake(), _fake(), 1 << 40, None) == cw.TTT_ERR_ARG
 
 
+def test_update_first_validation():
+    # the update-then-apply order: 0/1 only, not with the fused dot plan nor with kept states
+    lib = cw.lib()
+    s = cw.InplaceShape(1, 2048, 256, 512, 256, 4)
+    out = ctypes.c_size_t(0)
+    assert lib.ttt_inplace_workspace_bytes(ctypes.byref(s), cw.TTT_BF16, cw.TTT_MODE_DOT_SCAN, 0,
+                                           ctypes.byref(out)) == cw.TTT_OK
+    args = [_fake() for _ in range(3)]    # Z, Vhat, W_down0
+
+    def call(mode, opts):
+        return lib.ttt_core_apply_update_ex(ctypes.byref(s), cw.TTT_BF16, mode, 0.1, *args, ctypes.byref(opts),
+                                            _fake(), _fake(), _fake(), 1 << 40, None)
+
+    assert call(cw.TTT_MODE_MSE, cw.LayerOptions(None, 0, None, None, None, None, 2)) == cw.TTT_ERR_ARG
+    assert call(cw.TTT_MODE_DOT, cw.LayerOptions(None, 0, None, None, None, None, 1)) == cw.TTT_ERR_UNSUPPORTED
+    assert call(cw.TTT_MODE_MSE, cw.LayerOptions(None, 0, None, None, _fake(), None, 1)) == cw.TTT_ERR_UNSUPPORTED
+    lw = [_fake() for _ in range(7)]      # H, X0, W_gate, W_up, W_down0, W_target, conv_w
+    opts = cw.LayerOptions(None, 0, None, None, None, None, 1)
+    assert lib.ttt_chunk_apply_update_ex(ctypes.byref(s), cw.TTT_BF16, cw.TTT_MODE_DOT, 0.1, *lw, ctypes.byref(opts),
+                                         _fake(), _fake(), _fake(), 1 << 40, None) == cw.TTT_ERR_UNSUPPORTED
+
+
 def test_lact_validation():
     lib = cw.lib()
     out = ctypes.c_size_t(0)

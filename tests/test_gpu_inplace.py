@@ -377,6 +377,65 @@ def test_layer_resumed_in_two_calls(dtype, mode):
         assert rel(f64(W2[b]), Wref[b]) < tol and rel(f64(W2[b]) - W0, Wref[b] - W0) < tol, b
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["dot_scan", "mse"])
+def test_layer_update_first(dtype, mode):
+    """The update-then-apply order (update_first): each chunk is applied with the state after its own step,
+    against the oracle in that order, with every option it combines with.  Row 0 starts a document at chunk 0
+    (so it ignores W_init and x0_halo), row 1 resumes, masks chunks 1 and 4 and starts a document at chunk 3, row 2
+    resumes and masks chunk 0 (applied with W_init unchanged).  W_final is the apply-then-update call's, bit for
+    bit (the steps are the same arithmetic in both orders)."""
+    eta = 0.05 if mode != "mse" else 0.5
+    cfg = small_cfg(dtype, mode, B=3, n=1536, d=264, f=392, C=256, eta=eta)
+    k = cfg.seq_len // cfg.chunk
+    starts = np.zeros((3, k), dtype=np.uint8)
+    starts[0, 0] = 1
+    starts[1, 3] = 1
+    mask = np.ones((3, k), dtype=np.uint8)
+    mask[1, [1, 4]] = 0
+    mask[2, 0] = 0
+    x = ti.inplace_inputs(cfg)
+    r = ti.resume_inputs(cfg, seed=11)
+    g = dev(x)
+    args = tuple(g[n] for n in LAYER_W)
+    opts = dict(doc_starts=torch.from_numpy(starts).cuda(), update_mask=torch.from_numpy(mask).cuda(),
+                W_init=r["W_init"].cuda(), x0_halo=r["x0_halo"].cuda())
+    O, Wf = cw.ttt_chunk_apply_update(*args, cfg.chunk, cfg.eta, mode, update_first=True, **opts)
+    Oa, Wa = cw.ttt_chunk_apply_update(*args, cfg.chunk, cfg.eta, mode, **opts)
+    torch.cuda.synchronize()
+    assert torch.equal(Wf, Wa)
+    Oref, Wref = orc.inplace_layer(*(ti.to_f64(x[n]) for n in LAYER_W), cfg.chunk, cfg.eta,
+                                   "dot" if mode == "dot_scan" else mode, doc_starts=starts, update_mask=mask,
+                                   W_init=ti.to_f64(r["W_init"]), x0_halo=ti.to_f64(r["x0_halo"]),
+                                   update_first=True)
+    W0 = ti.to_f64(x["W_down0"])
+    for b in range(3):
+        assert rel(f64(O[b]), Oref[b]) < TOL[dtype], b
+        assert rel(f64(Wf[b]), Wref[b]) < TOL[dtype] and rel(f64(Wf[b]) - W0, Wref[b] - W0) < TOL[dtype], b
+    # row 2's first chunk is masked: in both orders it is applied with W_init
+    assert torch.equal(O[2, :cfg.chunk], Oa[2, :cfg.chunk])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", ["dot_scan", "mse"])
+def test_core_update_first(dtype, mode):
+    """The chunk loop given Z and V^ in the update-then-apply order, against the oracle's sequential definition
+    in that order, per row (ragged d and f, four chunks)."""
+    eta = 0.05 if mode != "mse" else 0.5
+    gz = torch.Generator().manual_seed(5)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    Z = (torch.randn(2, 1024, 392, generator=gz) * 0.6).to(tdt)
+    V = torch.randn(2, 1024, 264, generator=gz).to(tdt)
+    W0 = (torch.randn(264, 392, generator=gz) * 0.05).to(tdt)
+    O, Wf = cw.ttt_core_apply_update(Z.cuda(), V.cuda(), W0.cuda(), 256, eta, mode, update_first=True)
+    torch.cuda.synchronize()
+    for b in range(2):
+        Oref, Wref = orc.chunk_apply_update(ti.to_f64(Z[b]), ti.to_f64(V[b]), ti.to_f64(W0), 256, eta,
+                                            "dot" if mode == "dot_scan" else mode, update_first=True)
+        assert rel(f64(O[b]), Oref) < TOL[dtype], b
+        assert rel(f64(Wf[b]), Wref) < TOL[dtype], b
+
+
 def test_layer_bf16_chunk_not_multiple_of_kstep():
     # chunk 40: the dot plan falls back to materialised deltas + scan
     cfg = small_cfg("bf16", "dot", B=1, n=400, d=128, f=256, C=40, eta=0.02)
