@@ -394,6 +394,33 @@ __device__ __forceinline__ void mainloop(const OP& op, const OQ& oq, int nks, Ac
 #endif
 }
 
+// Steps k0 .. k1 - 1 only (the same loop, restarted at k0): a kernel may stop
+// the K loop, work on the accumulators outside it, and continue.
+template <typename T, class C, class OP, class OQ, class Hook, class Acc>
+__device__ __forceinline__ void mainloop_range(const OP& op, const OQ& oq, int k0, int k1, Acc& acc, char* smem,
+                                               const Hook& hook) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (k1 <= k0) return;
+  op.issue(k0, smem);
+  oq.issue(k0, smem + C::PBytes);
+  wait_dma();
+  __syncthreads();
+  for (int ks = k0; ks < k1; ++ks) {
+    const int i = ks - k0;
+    char* cur = smem + (i & 1) * C::Stage;
+    char* nxt = smem + ((i & 1) ^ 1) * C::Stage;
+    if (ks + 1 < k1) {
+      op.issue(ks + 1, nxt);
+      oq.issue(ks + 1, nxt + C::PBytes);
+    }
+    compute_stage<T, C, OP, OQ>(cur, cur + C::PBytes, acc);
+    wait_dma();
+    __syncthreads();
+    hook(ks, acc, cur);
+  }
+#endif
+}
+
 // ---------------------------------------------------------------- LDS-staged output
 
 // After the K loop the operand stages are free.  An output tile is assembled

@@ -7,6 +7,7 @@
 //   Zt [B, f, n]   read by the updates (K = tokens contiguous)
 //   Vt [B, d, n]   the target V^, transposed, read by the updates
 // so that every contraction reads both operands K-contiguously.
+#include <cstdlib>
 #include <type_traits>
 
 #include "gemm.hpp"
@@ -675,21 +676,56 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW
 // on a segment's states are absolute and the fix-up leaves them as they are.
 // The states are written with non-temporal stores: the apply reads them back
 // long after the caches would have dropped them.
+//
+// Chained segments (S = 2, `sync` given): the second segment does not leave
+// its states partial.  Segment 0 publishes its end state (Tot, fp32) through a
+// per-tile flag; segment 1 starts from zero and, at its first chunk boundary
+// (one chunk of tokens into its K loop), waits for the flag and adds the end
+// state to its accumulator, so that its states from there on are absolute and
+// are rounded once.  The workgroups are ordered so that this never waits for
+// long: each XCD runs its share of segment-0 tiles before the matching
+// segment-1 tiles, and a segment-1 tile's partner is the segment-0 tile of the
+// same state tile on the same XCD with a lower workgroup id, so the partner has
+// been dispatched before it (it is running or done) and itself waits for
+// nothing.  The wait is bounded (`wait` ticks of the 100 MHz wall clock,
+// negative: do not wait); a tile whose partner has not published in time
+// records that in its status word and keeps its states partial, and the
+// fix-up kernel that follows completes those tiles alone (then rounding them
+// twice).
+// One thread polls the flag; its acquire (which invalidates this CU's vector
+// cache, shared by the workgroup's waves) orders the workgroup's later reads
+// of the partner's end state after the flag, and the barrier hands the result
+// to every wave.
+__device__ __forceinline__ bool wait_published(const int* flag, long long wait, int* s_ok) {
+  if (threadIdx.x == 0) {
+    int v = 0;
+    if (wait >= 0) {
+      const long long t0 = wall_clock64();
+      while ((v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 0 &&
+             wall_clock64() - t0 < wait)
+        __builtin_amdgcn_s_sleep(8);
+    }
+    if (v != 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *s_ok = v;
+  }
+  __syncthreads();
+  return *s_ok != 0;
+}
+
 template <typename T>
 struct SnapshotHook {
-  T* Wc;              // [k, d, f] states of this batch row (segment 0)
+  T* Wc;              // [k, d, f] states of this batch row (segment 0, and chained segments)
   T* Wp;              // partial states of this batch row; chunk c at Wp + (c - kS) d f (later segments)
   const T* W0;        // W_down0, the state a packed document starts from
   const uint8_t* docs;  // document starts [B, k] or null
   int64_t b;
   int k, steps_per_chunk, c0, c1, kS, j0, i0, d, f;
+  bool chain;          // chained segments: every state goes to Wc
+  // Chunk boundary c (the state before chunk c): a document start resets the
+  // accumulator to W_down0, then the state is written.
   template <class A>
-  __device__ __forceinline__ void operator()(int ks, A& acc, char* free_stage) const {
-    const int done = ks + 1;
-    if (done % steps_per_chunk != 0) return;
-    const int c = c0 + done / steps_per_chunk;
-    if (c >= c1) return;
-    if (docs != nullptr && docs[b * k + c] != 0) {     // a document starts at chunk c: its state is absolute
+  __device__ __forceinline__ void boundary(int c, A& acc, char* buf, bool doc) const {
+    if (doc) {     // a document starts at chunk c: its state is absolute
       for_state_quads<Wide>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
         const f32x4 w = load4(W0 + ro + dj);
 #pragma unroll
@@ -697,8 +733,16 @@ struct SnapshotHook {
       });
     }
     const int64_t df = (int64_t)d * f;
-    T* dst = c0 == 0 ? Wc + (int64_t)c * df : Wp + (int64_t)(c - kS) * df;
-    stage_state<Wide, Wide::Stage, T, A, true>(acc, dst, free_stage, j0, i0, d, f);
+    T* dst = (c0 == 0 || chain) ? Wc + (int64_t)c * df : Wp + (int64_t)(c - kS) * df;
+    stage_state<Wide, Wide::Stage, T, A, true>(acc, dst, buf, j0, i0, d, f);
+  }
+  template <class A>
+  __device__ __forceinline__ void operator()(int ks, A& acc, char* free_stage) const {
+    const int done = ks + 1;
+    if (done % steps_per_chunk != 0) return;
+    const int c = c0 + done / steps_per_chunk;
+    if (c >= c1) return;
+    boundary(c, acc, free_stage, docs != nullptr && docs[b * k + c] != 0);
   }
 };
 
@@ -724,19 +768,41 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
                                                const T* __restrict__ W0, T* __restrict__ Wc, T* __restrict__ Wp,
                                                float* __restrict__ Tot, float* __restrict__ Wf, int n, int d, int f,
                                                int C_, int S, const uint8_t* __restrict__ docs,
-                                               const float* __restrict__ Winit) {
+                                               const float* __restrict__ Winit, int* __restrict__ sync,
+                                               int npairs, long long wait) {
   using G = Wide;
-  __shared__ __attribute__((aligned(16))) char smem[G::Smem];
+  // the operand stages, and one word past them for the chained segments' wait (a second LDS object would
+  // cost the K loop its alias information: the fragment reads would then wait for the next step's DMA)
+  __shared__ __attribute__((aligned(16))) char smem[G::Smem + 16];
+  int* s_ok = reinterpret_cast<int*>(smem + G::Smem);
   const int TP = (f + G::BP - 1) / G::BP, TQ = (d + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int bs = id / per;
-  const int b = bs / S, sg = bs - b * S;
+  const bool chain = sync != nullptr;
+  int b, sg, tile, pair = 0;
+  if (chain) {
+    // S = 2, chained: XCD x (workgroups x, x + 8, ...) takes a contiguous range
+    // of the npairs (batch row, state tile) pairs, first their segment-0 tiles,
+    // then their segment-1 tiles; the grid is padded to 16 ceil(npairs / 8)
+    const int x = (int)(blockIdx.x & 7), L = (int)(blockIdx.x >> 3);
+    const int q = npairs >> 3, r = npairs & 7;
+    const int np = q + (x < r ? 1 : 0), p0 = x * q + min(x, r);
+    if (L >= 2 * np) return;
+    sg = L >= np ? 1 : 0;
+    pair = p0 + L - sg * np;
+    b = pair / per;
+    tile = pair - b * per;
+  } else {
+    const int id = xcd_remap(blockIdx.x, gridDim.x);
+    const int bs = id / per;
+    b = bs / S;
+    sg = bs - b * S;
+    tile = id - bs * per;
+  }
   int tp, tq;
   // every d_model tile of one d_ff tile in one group: the tiles running at the
   // same time then read few distinct Zt rows, and each stretch of the token
   // stream is fetched from HBM about once rather than once per round
-  grouped_tile(id - bs * per, TP, TQ, TQ, tp, tq);
+  grouped_tile(tile, TP, TQ, TQ, tp, tq);
   const int k = n / C_, kS = k / S;
   const int c0 = sg * kS;
   const int j0 = tp * G::BP, i0 = tq * G::BQ;
@@ -776,18 +842,63 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
     });
     stage_state<G, G::Smem>(acc, wc, smem, j0, i0, d, f);                // chunk 0: W_down0 (or the resumed state)
   } else if (docs != nullptr && docs[(int64_t)b * k + c0] != 0) {
-    // a document starts with this segment: its states are absolute from the start (the fix-up writes chunk c0's)
+    // a document starts with this segment: its states are absolute from the start (chunk c0's state is
+    // written by the fix-up, or, chained, by segment 0)
     for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
       const f32x4 w = load4(W0 + ro + dj);
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
     });
   }
-  const SnapshotHook<T> hook{wc, Wp + (int64_t)b * (k - kS) * df, W0, docs, b, k, C_ * esz<T>() / 128, c0,
-                             c0 + kS, kS, j0, i0, d, f};
-  mainloop<T, G>(op, oq, (int)(kbytes / 128), acc, smem, hook);
+  const int spc = C_ * esz<T>() / 128, nks = (int)(kbytes / 128);
+  const SnapshotHook<T> hook{wc, Wp + (int64_t)b * (k - kS) * df, W0, docs, b, k, spc, c0, c0 + kS, kS, j0, i0, d,
+                             f, chain};
+  // Chained segment 1, not starting a document: its first chunk from zero, then the partner's end state is
+  // added at the first boundary, outside the K loop (so the loop's registers stay as they are), and its states
+  // from there on are absolute.  Every other tile runs the whole loop in the first range.
+  const bool split = chain && sg == 1 && !(docs != nullptr && docs[(int64_t)b * k + c0] != 0);
+  const SnapshotHook<T> hook1{wc, hook.Wp, W0, docs, b, k, spc, c0, split ? c0 + 1 : c0 + kS, kS, j0, i0, d, f,
+                              chain};
+  mainloop_range<T, G>(op, oq, 0, split ? spc : nks, acc, smem, hook1);
+  bool failed = false;
+  if (split) {
+    const bool doc = kS > 1 && docs != nullptr && docs[(int64_t)b * k + c0 + 1] != 0;
+    if (!doc) {
+      if (wait_published(sync + pair, wait, s_ok)) {
+        const float* tot = Tot + (int64_t)b * df;
+        for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+          const f32x4 t = load4(tot + ro + dj);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] += t[e];
+        });
+      } else {
+        failed = true;
+      }
+    }
+    if (kS > 1) hook.boundary(c0 + 1, acc, smem, doc);
+  }
+  mainloop_range<T, G>(op, oq, split ? spc : nks, nks, acc, smem, hook);
   float* out = sg == S - 1 ? Wf + (int64_t)b * df : Tot + ((int64_t)b * (S - 1) + sg) * df;
   stage_state<G, G::Smem>(acc, out, smem, j0, i0, d, f);
+  if (!chain) return;
+  if (sg == 0) {
+    // chunk kS's state (segment 1's first): this segment's end state, or W_down0 where a document starts there
+    if (docs != nullptr && docs[(int64_t)b * k + kS] != 0) {
+      for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+        const f32x4 w = load4(W0 + ro + dj);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
+      });
+    }
+    stage_state<G, G::Smem, T, decltype(acc), true>(acc, wc + (int64_t)kS * df, smem, j0, i0, d, f);
+    // publish: every wave waits for its stores of the end state (they are then in the XCD's L2), and one
+    // release store of the flag (which writes the L2 back for the other XCDs) follows them all
+    wait_dma();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(sync + pair, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (threadIdx.x == 0) {
+    sync[npairs + pair] = failed ? 1 : 0;    // the fix-up completes this tile
+  }
 }
 
 // Completes a segmented update-scan: adds to every partial state of segments
@@ -830,6 +941,49 @@ __global__ __launch_bounds__(256) void k_scan_fixup(T* __restrict__ Wc, const T*
     float* wf = Wf + (int64_t)b * df + e;
     const f32x4 w = load4(wf);
     store4(wf, w[0] + off[0], w[1] + off[1], w[2] + off[2], w[3] + off[3]);
+  }
+}
+
+// Completes the tiles of a chained update-scan (S = 2) whose segment 1 did not
+// receive its partner's end state in time (status word set): adds segment 0's
+// end state Tot to their partial states of chunks kS + 1 .. k - 1 (in place,
+// rounding them a second time) and to W_final, up to the first document start
+// in segment 1, from where they are absolute.  One workgroup per (batch row,
+// state tile) pair; the others return at once.
+template <typename T>
+__global__ __launch_bounds__(256) void k_chain_fixup(T* __restrict__ Wc, const float* __restrict__ Tot,
+                                                     float* __restrict__ Wf, const uint8_t* __restrict__ docs,
+                                                     const int* __restrict__ status, int k, int d, int f) {
+  if (status[blockIdx.x] == 0) return;
+  const int TP = (f + 255) / 256, TQ = (d + 255) / 256, per = TP * TQ;
+  const int b = (int)blockIdx.x / per, tile = (int)blockIdx.x - b * per;
+  int tp, tq;
+  grouped_tile(tile, TP, TQ, TQ, tp, tq);
+  const int j0 = tp * 256, i0 = tq * 256, kS = k / 2;
+  const int jn = min(256, f - j0), in_ = min(256, d - i0);
+  const int64_t df = (int64_t)d * f;
+  const float* tot = Tot + (int64_t)b * df;
+  int cend = k;                                   // chunks before the first document start after kS are partial
+  for (int c = kS + 1; c < k; ++c)
+    if (doc_start(docs, b, k, c)) {
+      cend = c;
+      break;
+    }
+  const int col = (threadIdx.x & 63) * 4;
+  for (int r = threadIdx.x >> 6; r < in_; r += 4) {
+    if (col >= jn) continue;                      // jn % 4 == 0
+    const int64_t o = (int64_t)(i0 + r) * f + j0 + col;
+    const f32x4 t = load4(tot + o);
+    for (int c = kS + 1; c < cend; ++c) {
+      T* w = Wc + ((int64_t)b * k + c) * df + o;
+      const f32x4 v = load4(w);
+      store4(w, v[0] + t[0], v[1] + t[1], v[2] + t[2], v[3] + t[3]);
+    }
+    if (cend == k) {
+      float* w = Wf + (int64_t)b * df + o;
+      const f32x4 v = load4(w);
+      store4(w, v[0] + t[0], v[1] + t[1], v[2] + t[2], v[3] + t[3]);
+    }
   }
 }
 
@@ -1350,26 +1504,62 @@ hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void k_zero_flags(int* __restrict__ p, int n) {
+  const int i = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (i < n) p[i] = 0;
+}
+
+// Wall-clock ticks a chained segment waits for its partner: 20 ms, or
+// TTT_UPDATE_SCAN_WAIT_US microseconds from the environment (negative: never
+// wait, so every tile takes the fix-up path -- for tests of that path).
+static long long chain_wait_ticks() {
+  long long us = 20000;
+  if (const char* v = std::getenv("TTT_UPDATE_SCAN_WAIT_US")) us = std::atoll(v);
+  if (us < 0) return -1;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) !=
+      hipSuccess || khz <= 0)
+    khz = 100000;
+  return us * khz / 1000;
+}
+
 template <typename T>
 hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
                                     int B, int n, int d, int f, int Cs, int S, const uint8_t* docs,
                                     const float* Winit, hipStream_t s, int layout) {
-  const int64_t tiles = cdiv(f, kWB) * cdiv(d, kWB) * B * S;
+  const int64_t per = cdiv(f, kWB) * cdiv(d, kWB);
+  const int64_t tiles = per * B * S;
   if (tiles == 0) return hipSuccess;
+  // Two segments are chained (no partial states) when the partial-state space
+  // holds the flags and status words: 2 npairs ints.
+  const int k = n / Cs;
+  const int64_t npairs = per * B;
+  const bool chain = S == 2 && (int64_t)B * (k - k / 2) * d * f * (int64_t)sizeof(T) >= 8 * npairs;
+  int* sync = chain ? reinterpret_cast<int*>(Wp) : nullptr;
+  const long long wait = chain ? chain_wait_ticks() : 0;
+  const unsigned grid = chain ? tiles_u(16 * cdiv(npairs, 8)) : tiles_u(tiles);
+  if (chain) {
+    k_zero_flags<<<(unsigned)cdiv(npairs, 256), 256, 0, s>>>(sync, (int)npairs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+#define TTT_SCAN_ARGS Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f, Cs, S, docs, Winit, sync, (int)npairs, wait
   if (layout == kScanRowMajorReversed)
-    k_chunk_update_scan<T, true, true><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f, Cs,
-                                                                           S, docs, Winit);
+    k_chunk_update_scan<T, true, true><<<grid, Wide::NT, 0, s>>>(TTT_SCAN_ARGS);
   else if (layout == kScanRowMajor)
-    k_chunk_update_scan<T, true, false><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f,
-                                                                            Cs, S, docs, Winit);
+    k_chunk_update_scan<T, true, false><<<grid, Wide::NT, 0, s>>>(TTT_SCAN_ARGS);
   else
-    k_chunk_update_scan<T, false, false><<<tiles_u(tiles), Wide::NT, 0, s>>>(Zt, Vt, W0, Wc, Wp, Tot, Wf, n, d, f,
-                                                                             Cs, S, docs, Winit);
+    k_chunk_update_scan<T, false, false><<<grid, Wide::NT, 0, s>>>(TTT_SCAN_ARGS);
+#undef TTT_SCAN_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
+  if (chain) {
+    k_chain_fixup<T><<<(unsigned)npairs, 256, 0, s>>>(Wc, Tot, Wf, docs, sync + npairs, k, d, f);
+    return hipGetLastError();
+  }
   const int64_t df = (int64_t)d * f;
-  k_scan_fixup<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(Wc, Wp, Tot, Wf, W0, docs, n / Cs,
-                                                                                  S, df);
+  k_scan_fixup<T><<<dim3((unsigned)cdiv(df / 4, 256), (unsigned)B), 256, 0, s>>>(Wc, Wp, Tot, Wf, W0, docs, k, S,
+                                                                                  df);
   return hipGetLastError();
 }
 

@@ -39,20 +39,24 @@ hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc
 // Number of sequence segments the fused update-scan runs side by side (a
 // segment count divides the chunk count), by a two-term cost model: the K loop
 // takes ceil(tiles S / 256) rounds of k C / S tokens at about 28 ns per token
-// and round, and the fix-up pass reads and writes the (k - k / S) partial
-// states of the later segments, 4 bytes per state element at about 5.5 TB/s.
-// Both rates are measured on the 128K workload (2560 x 9728 state, 380 tiles):
-// with 4096-token chunks two segments win (three rounds of half-length tiles
-// against two of full length), with 512-token chunks one does (the fix-up over
-// 128 partial states costs more than the rounds save).  The count depends on
-// the state's and the sequence's shape alone, so a batch row's summation
-// order, and with it every bit of its result, does not depend on the other
-// rows of the batch.
+// and round, and with four segments the fix-up pass reads and writes the
+// (k - k / S) partial states of the later segments, 4 bytes per state element
+// at about 5.5 TB/s.  Two segments are chained instead (the second takes the
+// first's end state one chunk into its K loop, no partial states): no fix-up,
+// but at least two rounds, since a second-segment tile that runs beside its
+// partner waits for it.  Both rates are measured on the 128K workload (2560 x
+// 9728 state, 380 tiles): two chained segments give three rounds of
+// half-length tiles against two of full length.  The count depends on the
+// state's and the sequence's shape alone, so a batch row's summation order,
+// and with it every bit of its result, does not depend on the other rows of
+// the batch.
 inline int update_scan_segments(int64_t d, int64_t f, int64_t k, int64_t C) {
   const int64_t tiles = ((f + 255) / 256) * ((d + 255) / 256);
   auto cost = [&](int64_t S) {
-    const double rounds = (double)((tiles * S + 255) / 256);
-    return rounds * (double)(k * C / S) * 28.1e-9 + (double)(k - k / S) * (double)(d * f) * 4.0 / 5.5e12;
+    const int64_t r = (tiles * S + 255) / 256;
+    const double rounds = (double)(S == 2 && r < 2 ? 2 : r);
+    const double fixup = S > 2 ? (double)(k - k / S) * (double)(d * f) * 4.0 / 5.5e12 : 0.0;
+    return rounds * (double)(k * C / S) * 28.1e-9 + fixup;
   };
   int S = 1;
   for (int cand : {2, 4})

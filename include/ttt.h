@@ -507,11 +507,19 @@ int ttt_update_scan_workspace_bytes(const ttt_inplace_shape* shape, int dtype, s
  * last chunk W_final.  When the state has too few tiles to fill the GPU, the
  * sequence may run as S side-by-side segments (S in {1, 2, 4} dividing the
  * chunk count, chosen from d_model, d_ff, chunk and the chunk count alone by
- * weighing the rounds of tiles against the pass below), and a short elementwise pass adds
- * the earlier segments' totals (fp32) to the later segments' partial states
- * (kept in dtype; with bf16 a state of a later segment is thus rounded twice);
+ * weighing the rounds of tiles against the cost of joining the segments).
+ * S = 2: each second-segment tile takes the first segment's end state (fp32)
+ * of the same state tile inside the kernel, one chunk into its K loop, so
+ * every state is rounded once.  That wait is bounded (20 ms, or
+ * TTT_UPDATE_SCAN_WAIT_US microseconds read from the environment at each call;
+ * negative: no wait); a tile that does not receive the end state in time keeps
+ * partial states, which a short pass after the kernel completes (rounding
+ * them twice in bf16).  S = 4: a short elementwise pass adds the earlier
+ * segments' totals (fp32) to the later segments' partial states (kept in
+ * dtype; with bf16 a state of a later segment is thus rounded twice).
  * `workspace` (device, at least ttt_update_scan_workspace_bytes) holds the
- * partial states and may be NULL when that query returns 0.
+ * partial states (S = 4; with S = 2 two flag words per state tile in their
+ * place) and the totals, and may be NULL when that query returns 0.
  * Same outputs as ttt_chunk_delta (on the unscaled target) followed by
  * ttt_chunk_scan with eta, without dW. */
 int ttt_chunk_update_scan(const ttt_inplace_shape* shape, int dtype, const void* W_down0, const void* Zt,

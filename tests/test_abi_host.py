@@ -82,16 +82,20 @@ def _update_scan_ws(shape, dtype=cw.TTT_BF16):
 
 def test_update_scan_segments_and_workspace():
     """The fused update-scan runs the sequence as S segments (S in 1, 2, 4 dividing the chunk count) when
-    the model of its time -- rounds of 256 tiles times tokens per segment, plus the fix-up pass over the
-    later segments' partial states -- says so (S depends on the state's and the sequence's shape only, so
-    rows do not depend on the batch they are in); its scratch holds the partial states of chunks past the
-    first segment (bf16 here) and the S - 1 fp32 segment totals."""
+    the model of its time -- rounds of 256 tiles times tokens per segment, with four segments plus the fix-up
+    pass over the later segments' partial states, with two (chained) at least two rounds -- says so (S depends
+    on the state's and the sequence's shape only, so rows do not depend on the batch they are in); its scratch
+    holds the partial states of chunks past the first segment (bf16 here) and the S - 1 fp32 segment totals."""
     al = lambda x: (x + 255) // 256 * 256
 
     def expect(B, n, d, f, C):
         k = n // C
         tiles = -(-f // 256) * -(-d // 256)
-        cost = lambda S: -(-tiles * S // 256) * (k * C // S) * 28.1e-9 + (k - k // S) * d * f * 4.0 / 5.5e12
+        def cost(S):
+            rounds = -(-tiles * S // 256)
+            if S == 2:
+                rounds = max(rounds, 2)
+            return rounds * (k * C // S) * 28.1e-9 + ((k - k // S) * d * f * 4.0 / 5.5e12 if S > 2 else 0.0)
         S = 1
         for cand in (2, 4):
             if k % cand == 0 and cost(cand) < cost(S):
@@ -100,7 +104,7 @@ def test_update_scan_segments_and_workspace():
 
     cases = [(1, 131072, 2560, 9728, 4096, 2), (1, 32768, 2560, 9728, 1024, 2), (1, 2048, 1024, 4096, 256, 4),
              (2, 1024, 1024, 4096, 128, 4), (1, 2048, 256, 512, 256, 4), (4, 65536, 2048, 8192, 2048, 1),
-             (1, 131072, 2560, 9728, 512, 1),    # 256 short chunks: the fix-up would cost more than it saves
+             (1, 131072, 2560, 9728, 512, 2),    # 256 short chunks: chained, no fix-up over 128 partial states
              (1, 4096, 2560, 9728, 4096, 1)]     # one chunk: nothing to split
     for B, n, d, f, C, S in cases:
         s_exp, ws = expect(B, n, d, f, C)

@@ -128,14 +128,15 @@ def test_fused_update_scan_matches_materialised(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("B,n,d,f,C,segments", [
-    (1, 2048, 1024, 4096, 256, 4),     # 64 state tiles: four sequence segments
+    (1, 2048, 1024, 4096, 256, 4),     # 64 state tiles: four sequence segments and the fix-up pass
     (2, 1024, 1024, 4096, 128, 4),     # two batch rows of 64 tiles: four segments each
-    (1, 1024, 2560, 2560, 256, 2),     # 100 tiles: two segments
+    (1, 1024, 2560, 6656, 256, 2),     # 260 tiles: two chained segments (three rounds of tiles)
+    (2, 512, 2560, 6656, 256, 2),      # two rows, one chunk per chained segment
 ])
 def test_segmented_update_scan(dtype, B, n, d, f, C, segments):
-    """The fused update-scan cut into sequence segments (plus the fix-up pass) equals the materialised
-    deltas + scan and the oracle's prefix form; the partial states of later segments receive the
-    earlier segments' totals."""
+    """The fused update-scan cut into sequence segments equals the materialised deltas + scan and the oracle's
+    prefix form: with four segments the later segments' partial states receive the earlier totals in the fix-up
+    pass, with two the second segment takes the first's end state inside the kernel."""
     shape = cw.InplaceShape(B, n, d, f, C, 1)
     k = n // C
     DF = d * f
@@ -162,6 +163,41 @@ def test_segmented_update_scan(dtype, B, n, d, f, C, segments):
         for c in range(k):
             _, Wc_ref = orc.chunk_prefix_form(Zn[b, : c * C], Vsn[b, : c * C], W0n, C, 1.0) if c else (None, W0n)
             assert rel(Wcs[c], Wc_ref) < STEP_TOL[dtype], (b, c)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("fallback", [False, True])
+def test_chained_segments_with_documents(dtype, fallback, monkeypatch):
+    """Two chained segments (260 state tiles, 8 chunks, segment 1 from chunk 4) on the chunk loop given Z and V^
+    (dot objective, fused plan), with documents starting further into segment 1 (row 0), at its first chunk (row
+    1) and one chunk into it (row 2), and none (row 3), against the oracle run per document.  With the wait
+    disabled (TTT_UPDATE_SCAN_WAIT_US=-1) every segment-1 tile keeps partial states and the fix-up kernel
+    completes it: the same results up to rounding."""
+    B, n, d, f, C, eta = 4, 2048, 2560, 6656, 256, 0.02
+    k = n // C
+    starts = np.zeros((B, k), dtype=np.uint8)
+    starts[0, 6] = 1
+    starts[1, 4] = 1
+    starts[2, 5] = 1
+    Z, V, W0 = _zv(dtype, B, n, d, f, 41)
+    g = (Z.cuda(), V.cuda(), W0.cuda())
+    if fallback:
+        monkeypatch.setenv("TTT_UPDATE_SCAN_WAIT_US", "-1")
+    O, Wf = cw.ttt_core_apply_update(*g, C, eta, "dot", doc_starts=torch.from_numpy(starts).cuda())
+    torch.cuda.synchronize()
+    W0n = f64(W0)
+    for b in range(B):
+        bounds = [0] + [c for c in range(1, k) if starts[b, c]] + [k]
+        for s0, e0 in zip(bounds[:-1], bounds[1:]):
+            Oref, Wref = orc.chunk_apply_update(f64(Z[b, s0 * C:e0 * C]), f64(V[b, s0 * C:e0 * C]), W0n, C, eta,
+                                                "dot")
+            assert rel(f64(O[b, s0 * C:e0 * C]), Oref) < TOL[dtype], (b, s0)
+        assert rel(f64(Wf[b]), Wref) < TOL[dtype] and rel(f64(Wf[b]) - W0n, Wref - W0n) < TOL[dtype], b
+    if fallback:
+        monkeypatch.delenv("TTT_UPDATE_SCAN_WAIT_US")
+        O2, Wf2 = cw.ttt_core_apply_update(*g, C, eta, "dot", doc_starts=torch.from_numpy(starts).cuda())
+        torch.cuda.synchronize()
+        assert rel(f64(O), f64(O2)) < STEP_TOL[dtype] and rel(f64(Wf), f64(Wf2)) < STEP_TOL[dtype]
 
 
 # ---------------------------------------------------------------- whole layer
@@ -615,8 +651,8 @@ def test_full_size_32k():
 
 @pytest.mark.slow
 def test_full_size_128k():
-    """128K tokens, chunk 4096: the bench's workload.  The fused scan runs two sequence segments, so chunks 17-31
-    are applied with later-segment states that carry the fix-up's offset (rounded twice in bf16)."""
+    """128K tokens, chunk 4096: the bench's workload.  The fused scan runs two chained sequence segments, so chunks
+    17-31 are applied with states the second segment formed from the first's end state."""
     _full_size("inplace_bf16_128k")
 
 
