@@ -696,6 +696,16 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW
 // cache, shared by the workgroup's waves) orders the workgroup's later reads
 // of the partner's end state after the flag, and the barrier hands the result
 // to every wave.
+// Tile raster of the chained scan: groups of about 5 d_model tiles, each
+// swept across the d_ff tiles, so that the 32 tiles an XCD runs at once (and
+// the two half-rounds of first- and second-segment tiles it runs together)
+// form compact blocks that share operand rows in its L2 (5 x 6 rather than
+// 10 x 3 tiles).
+__device__ __forceinline__ int chain_group(int TQ) {
+  const int g = (TQ + 4) / 5;
+  return (TQ + g - 1) / g;
+}
+
 __device__ __forceinline__ bool wait_published(const int* flag, long long wait, int* s_ok) {
   if (threadIdx.x == 0) {
     int v = 0;
@@ -799,10 +809,11 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
     tile = id - bs * per;
   }
   int tp, tq;
-  // every d_model tile of one d_ff tile in one group: the tiles running at the
-  // same time then read few distinct Zt rows, and each stretch of the token
-  // stream is fetched from HBM about once rather than once per round
-  grouped_tile(tile, TP, TQ, TQ, tp, tq);
+  // unchained: every d_model tile of one d_ff tile in one group: the tiles
+  // running at the same time then read few distinct Zt rows, and each stretch
+  // of the token stream is fetched from HBM about once rather than once per
+  // round; chained: chain_group
+  grouped_tile(tile, TP, TQ, chain ? chain_group(TQ) : TQ, tp, tq);
   const int k = n / C_, kS = k / S;
   const int c0 = sg * kS;
   const int j0 = tp * G::BP, i0 = tq * G::BQ;
@@ -958,7 +969,7 @@ __global__ __launch_bounds__(256) void k_chain_fixup(T* __restrict__ Wc, const f
   const int TP = (f + 255) / 256, TQ = (d + 255) / 256, per = TP * TQ;
   const int b = (int)blockIdx.x / per, tile = (int)blockIdx.x - b * per;
   int tp, tq;
-  grouped_tile(tile, TP, TQ, TQ, tp, tq);
+  grouped_tile(tile, TP, TQ, chain_group(TQ), tp, tq);
   const int j0 = tp * 256, i0 = tq * 256, kS = k / 2;
   const int jn = min(256, f - j0), in_ = min(256, d - i0);
   const int64_t df = (int64_t)d * f;
