@@ -105,6 +105,19 @@ __device__ __forceinline__ int group_sync_tile(int bid, int total, int per) {
   return (i / px) * per + (bid & 7) * px + (i % px);
 }
 
+// Runs of R consecutive tiles dealt round-robin to the XCDs: XCD x takes runs
+// x, x + 8, x + 16, ...  At any time the GPU works on about 8 consecutive runs
+// (one round of tiles when R is the CUs of an XCD), and the R tiles an XCD
+// runs together are one run, which a grouped raster makes a compact block of
+// tiles sharing operand rows in that XCD's L2.  A tail of fewer than 8 R tiles
+// keeps the dispatch order.
+__device__ __forceinline__ int xcd_runs(int bid, int total, int R) {
+  const int full = total / (8 * R) * (8 * R);
+  if (bid >= full) return bid;
+  const int L = bid >> 3;
+  return ((L / R) * 8 + (bid & 7)) * R + L % R;
+}
+
 // Grouped raster over a TP x TQ grid: groups of G q-tiles, p fastest inside a
 // group, so a run of consecutive ids covers a compact block of tiles.
 __device__ __forceinline__ void grouped_tile(int id, int TP, int TQ, int G, int& tp, int& tq) {

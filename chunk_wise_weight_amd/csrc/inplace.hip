@@ -1012,10 +1012,13 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
   __shared__ __attribute__((aligned(16))) char smem[G::Smem];
   const int TP = (d + G::BP - 1) / G::BP, TQ = (C_ + G::BQ - 1) / G::BQ;
   const int per = TP * TQ;
-  const int id = group_sync_tile(blockIdx.x, gridDim.x, per);     // all XCDs on one chunk at a time
+  // chunks of at least 128 tiles: runs of 32 tiles (an XCD's round) in groups of 8 token tiles, 4 x 8 blocks
+  // (the whole GPU on about 1.6 chunks at a time); smaller chunks: the plain XCD order
+  const bool big = per >= 128;
+  const int id = big ? xcd_runs(blockIdx.x, gridDim.x, 32) : xcd_remap(blockIdx.x, gridDim.x);
   const int bc = id / per;
   int tp, tq;
-  grouped_tile(id - bc * per, TP, TQ, 4, tp, tq);
+  grouped_tile(id - bc * per, TP, TQ, big ? 8 : 4, tp, tq);
   const int k = n / C_;
   const int b = bc / k, c = bc - b * k;
   const int i0 = tp * G::BP, t0 = tq * G::BQ;
