@@ -666,11 +666,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan(const float* __restrict__ dW
 //
 // To fill the chip when the state has few tiles, the sequence is cut into S
 // segments of k / S chunks that run side by side.  Segment 0 starts from
-// W_down0 and writes the states W_c of its chunks in the operand dtype; a
-// later segment starts from zero and writes partial states to Wp (operand dtype)
-// (chunks after its first) and its total to Tot[b, s - 1] -- except the last
-// segment, whose total goes to W_final.  k_scan_fixup then adds the earlier
-// segments' totals.  With S = 1 the kernel alone produces every output.
+// W_down0 and writes the states W_c of its chunks in the operand dtype.  Two
+// segments are chained (below).  With four, a later segment starts from zero
+// and writes partial states to Wp (operand dtype) (chunks after its first) and
+// its total to Tot[b, s - 1] -- except the last segment, whose total goes to
+// W_final -- and k_scan_fixup then adds the earlier segments' totals.  With
+// S = 1 the kernel alone produces every output.
 // With packed documents the accumulator is set to W_down0 at every document
 // start (a segment that begins with one starts from W_down0), so from there
 // on a segment's states are absolute and the fix-up leaves them as they are.
