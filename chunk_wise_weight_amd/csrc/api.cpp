@@ -177,7 +177,8 @@ int run_core(const Plan& p, int mode, float eta, const void* Ztv, const void* Vt
   int st;
   if (p.fused) {
     st = dev(ttt::launch_chunk_update_scan<T>(Zt, Vt, W0, Wc, Wf, (T*)(ws + p.off_Wp), (float*)(ws + p.off_Tot),
-                                              B, n, d, f, C, p.S, p.docs, p.Winit, s));   // Vt carries eta
+                                              B, n, d, f, C, p.S, p.docs, p.Winit, s, ttt::kScanTokenContiguous,
+                                              p.update_first));   // Vt carries eta
   } else {
     float* dW = (float*)(ws + p.off_dW);
     st = dev(ttt::launch_chunk_delta<T>(Zt, Vt, dW, B, n, d, f, C, s));
@@ -213,8 +214,11 @@ int apply_options(Plan& p, int mode, const ttt_layer_options* o, bool producers)
   if (o == nullptr) return TTT_OK;
   if (producers && o->conv_forward != 0 && o->conv_forward != 1) return TTT_ERR_ARG;
   if (o->update_first != 0 && o->update_first != 1) return TTT_ERR_ARG;
-  if (o->update_first == 1 && (mode == TTT_MODE_DOT || o->W_states != nullptr)) return TTT_ERR_UNSUPPORTED;
+  if (o->update_first == 1 && o->W_states != nullptr) return TTT_ERR_UNSUPPORTED;
   p.update_first = o->update_first == 1;
+  // the fused plan writes the states after each chunk's step with one or two (chained) segments; four fall back
+  // to one (its workspace holds less than the four-segment plan's)
+  if (p.update_first && p.fused && p.S > 2) p.S = 1;
   if ((o->W_init != nullptr && !ok_ptr(o->W_init)) || (producers && o->x0_halo != nullptr && !ok_ptr(o->x0_halo)) ||
       (o->W_states != nullptr && !ok_ptr(o->W_states)))
     return TTT_ERR_ARG;

@@ -723,7 +723,11 @@ __device__ __forceinline__ bool wait_published(const int* flag, long long wait, 
   return *s_ok != 0;
 }
 
-template <typename T>
+// INC (the update-then-apply order): the state written for chunk c is the one
+// after its own step, W_{c+1}: at boundary c the accumulator is written as
+// chunk c - 1's state before a document start at c resets it, and a segment
+// ends by writing its last chunk's; no initial state is written.
+template <typename T, bool INC = false>
 struct SnapshotHook {
   T* Wc;              // [k, d, f] states of this batch row (segment 0, and chained segments)
   T* Wp;              // partial states of this batch row; chunk c at Wp + (c - kS) d f (later segments)
@@ -732,20 +736,25 @@ struct SnapshotHook {
   int64_t b;
   int k, steps_per_chunk, c0, c1, kS, j0, i0, d, f;
   bool chain;          // chained segments: every state goes to Wc
+  template <class A>
+  __device__ __forceinline__ void reset(A& acc) const {
+    for_state_quads<Wide>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
+      const f32x4 w = load4(W0 + ro + dj);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
+    });
+  }
   // Chunk boundary c (the state before chunk c): a document start resets the
-  // accumulator to W_down0, then the state is written.
+  // accumulator to W_down0, then the state is written (INC: the state is
+  // written as chunk c - 1's first).
   template <class A>
   __device__ __forceinline__ void boundary(int c, A& acc, char* buf, bool doc) const {
-    if (doc) {     // a document starts at chunk c: its state is absolute
-      for_state_quads<Wide>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
-        const f32x4 w = load4(W0 + ro + dj);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
-      });
-    }
+    if (!INC && doc) reset(acc);     // a document starts at chunk c: its state is absolute
     const int64_t df = (int64_t)d * f;
-    T* dst = (c0 == 0 || chain) ? Wc + (int64_t)c * df : Wp + (int64_t)(c - kS) * df;
+    const int slot = INC ? c - 1 : c;
+    T* dst = (c0 == 0 || chain) ? Wc + (int64_t)slot * df : Wp + (int64_t)(slot - kS) * df;
     stage_state<Wide, Wide::Stage, T, A, true>(acc, dst, buf, j0, i0, d, f);
+    if (INC && doc) reset(acc);
   }
   template <class A>
   __device__ __forceinline__ void operator()(int ks, A& acc, char* free_stage) const {
@@ -774,7 +783,7 @@ struct RevChunks : OP {
 // copies [B, f, n] and [B, d, n].  REV (with NAT): the chunks are scanned in
 // reverse order, last chunk first; state index c then names the c-th chunk of
 // that order.
-template <typename T, bool NAT, bool REV>
+template <typename T, bool NAT, bool REV, bool INC = false>
 TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T* __restrict__ Vt,
                                                const T* __restrict__ W0, T* __restrict__ Wc, T* __restrict__ Wp,
                                                float* __restrict__ Tot, float* __restrict__ Wf, int n, int d, int f,
@@ -822,6 +831,7 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
   const unsigned kbytes = (unsigned)kS * C_ * esz<T>();
 
   static_assert(NAT || !REV, "the reversed order reads the row-major operands");
+  static_assert(!INC || !NAT, "the update-then-apply states: the forward layout");
   using OPP = std::conditional_t<NAT, DmaOpMN<T, G::NW, G::BP>, DmaOp<G::NW, G::BP>>;
   using OPQ = std::conditional_t<NAT, DmaOpMN<T, G::NW, G::BQ>, DmaOp<G::NW, G::BQ>>;
   std::conditional_t<REV, RevChunks<OPP>, OPP> op;
@@ -852,7 +862,7 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
     });
-    stage_state<G, G::Smem>(acc, wc, smem, j0, i0, d, f);                // chunk 0: W_down0 (or the resumed state)
+    if (!INC) stage_state<G, G::Smem>(acc, wc, smem, j0, i0, d, f);     // chunk 0: W_down0 (or the resumed state)
   } else if (docs != nullptr && docs[(int64_t)b * k + c0] != 0) {
     // a document starts with this segment: its states are absolute from the start (chunk c0's state is
     // written by the fix-up, or, chained, by segment 0)
@@ -863,19 +873,20 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
     });
   }
   const int spc = C_ * esz<T>() / 128, nks = (int)(kbytes / 128);
-  const SnapshotHook<T> hook{wc, Wp + (int64_t)b * (k - kS) * df, W0, docs, b, k, spc, c0, c0 + kS, kS, j0, i0, d,
-                             f, chain};
+  const SnapshotHook<T, INC> hook{wc, Wp + (int64_t)b * (k - kS) * df, W0, docs, b, k, spc, c0, c0 + kS, kS, j0,
+                                  i0, d, f, chain};
   // Chained segment 1, not starting a document: its first chunk from zero, then the partner's end state is
   // added at the first boundary, outside the K loop (so the loop's registers stay as they are), and its states
   // from there on are absolute.  Every other tile runs the whole loop in the first range.
   const bool split = chain && sg == 1 && !(docs != nullptr && docs[(int64_t)b * k + c0] != 0);
-  const SnapshotHook<T> hook1{wc, hook.Wp, W0, docs, b, k, spc, c0, split ? c0 + 1 : c0 + kS, kS, j0, i0, d, f,
-                              chain};
+  const SnapshotHook<T, INC> hook1{wc, hook.Wp, W0, docs, b, k, spc, c0, split ? c0 + 1 : c0 + kS, kS, j0, i0, d, f,
+                                   chain};
   mainloop_range<T, G>(op, oq, 0, split ? spc : nks, acc, smem, hook1);
   bool failed = false;
   if (split) {
     const bool doc = kS > 1 && docs != nullptr && docs[(int64_t)b * k + c0 + 1] != 0;
-    if (!doc) {
+    // INC writes chunk c0's state before a reset at c0 + 1, so it always needs the end state
+    if (INC || !doc) {
       if (wait_published(sync + pair, wait, s_ok)) {
         const float* tot = Tot + (int64_t)b * df;
         for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
@@ -892,17 +903,20 @@ TTT_GEMM_KERNEL(Wide) void k_chunk_update_scan(const T* __restrict__ Zt, const T
   mainloop_range<T, G>(op, oq, split ? spc : nks, nks, acc, smem, hook);
   float* out = sg == S - 1 ? Wf + (int64_t)b * df : Tot + ((int64_t)b * (S - 1) + sg) * df;
   stage_state<G, G::Smem>(acc, out, smem, j0, i0, d, f);
+  // INC: the segment's last chunk's state (one or two segments: in Wc)
+  if (INC) stage_state<G, G::Smem, T, decltype(acc), true>(acc, wc + (int64_t)(c0 + kS - 1) * df, smem, j0, i0, d, f);
   if (!chain) return;
   if (sg == 0) {
     // chunk kS's state (segment 1's first): this segment's end state, or W_down0 where a document starts there
-    if (docs != nullptr && docs[(int64_t)b * k + kS] != 0) {
+    // (INC: segment 1 writes every state of its own chunks)
+    if (!INC && docs != nullptr && docs[(int64_t)b * k + kS] != 0) {
       for_state_quads<G>(j0, i0, d, f, [&](int64_t ro, int dj, int ib, int jb, int g) {
         const f32x4 w = load4(W0 + ro + dj);
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[ib][jb][4 * g + e] = w[e];
       });
     }
-    stage_state<G, G::Smem, T, decltype(acc), true>(acc, wc + (int64_t)kS * df, smem, j0, i0, d, f);
+    if (!INC) stage_state<G, G::Smem, T, decltype(acc), true>(acc, wc + (int64_t)kS * df, smem, j0, i0, d, f);
     // publish: every wave waits for its stores of the end state (they are then in the XCD's L2), and one
     // release store of the flag (which writes the L2 back for the other XCDs) follows them all
     wait_dma();
@@ -958,14 +972,16 @@ __global__ __launch_bounds__(256) void k_scan_fixup(T* __restrict__ Wc, const T*
 
 // Completes the tiles of a chained update-scan (S = 2) whose segment 1 did not
 // receive its partner's end state in time (status word set): adds segment 0's
-// end state Tot to their partial states of chunks kS + 1 .. k - 1 (in place,
-// rounding them a second time) and to W_final, up to the first document start
-// in segment 1, from where they are absolute.  One workgroup per (batch row,
+// end state Tot to their partial states of chunks kS + 1 .. k - 1 (inc: the
+// states after each chunk's step, kS .. k - 1) in place, rounding them a
+// second time, and to W_final, up to the first document start in segment 1,
+// from where they are absolute.  One workgroup per (batch row,
 // state tile) pair; the others return at once.
 template <typename T>
 __global__ __launch_bounds__(256) void k_chain_fixup(T* __restrict__ Wc, const float* __restrict__ Tot,
                                                      float* __restrict__ Wf, const uint8_t* __restrict__ docs,
-                                                     const int* __restrict__ status, int k, int d, int f) {
+                                                     const int* __restrict__ status, int k, int d, int f,
+                                                     bool inc) {
   if (status[blockIdx.x] == 0) return;
   const int TP = (f + 255) / 256, TQ = (d + 255) / 256, per = TP * TQ;
   const int b = (int)blockIdx.x / per, tile = (int)blockIdx.x - b * per;
@@ -986,7 +1002,7 @@ __global__ __launch_bounds__(256) void k_chain_fixup(T* __restrict__ Wc, const f
     if (col >= jn) continue;                      // jn % 4 == 0
     const int64_t o = (int64_t)(i0 + r) * f + j0 + col;
     const f32x4 t = load4(tot + o);
-    for (int c = kS + 1; c < cend; ++c) {
+    for (int c = inc ? kS : kS + 1; c < cend; ++c) {
       T* w = Wc + ((int64_t)b * k + c) * df + o;
       const f32x4 v = load4(w);
       store4(w, v[0] + t[0], v[1] + t[1], v[2] + t[2], v[3] + t[3]);
@@ -1541,15 +1557,17 @@ static long long chain_wait_ticks() {
 template <typename T>
 hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
                                     int B, int n, int d, int f, int Cs, int S, const uint8_t* docs,
-                                    const float* Winit, hipStream_t s, int layout) {
+                                    const float* Winit, hipStream_t s, int layout, bool inclusive) {
   const int64_t per = cdiv(f, kWB) * cdiv(d, kWB);
   const int64_t tiles = per * B * S;
   if (tiles == 0) return hipSuccess;
+  if (inclusive && (S > 2 || layout != kScanTokenContiguous)) return hipErrorInvalidValue;
   // Two segments are chained (no partial states) when the partial-state space
   // holds the flags and status words: 2 npairs ints.
   const int k = n / Cs;
   const int64_t npairs = per * B;
   const bool chain = S == 2 && (int64_t)B * (k - k / 2) * d * f * (int64_t)sizeof(T) >= 8 * npairs;
+  if (inclusive && S == 2 && !chain) return hipErrorInvalidValue;
   int* sync = chain ? reinterpret_cast<int*>(Wp) : nullptr;
   const long long wait = chain ? chain_wait_ticks() : 0;
   const unsigned grid = chain ? tiles_u(16 * cdiv(npairs, 8)) : tiles_u(tiles);
@@ -1563,13 +1581,15 @@ hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc
     k_chunk_update_scan<T, true, true><<<grid, Wide::NT, 0, s>>>(TTT_SCAN_ARGS);
   else if (layout == kScanRowMajor)
     k_chunk_update_scan<T, true, false><<<grid, Wide::NT, 0, s>>>(TTT_SCAN_ARGS);
+  else if (inclusive)
+    k_chunk_update_scan<T, false, false, true><<<grid, Wide::NT, 0, s>>>(TTT_SCAN_ARGS);
   else
     k_chunk_update_scan<T, false, false><<<grid, Wide::NT, 0, s>>>(TTT_SCAN_ARGS);
 #undef TTT_SCAN_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   if (chain) {
-    k_chain_fixup<T><<<(unsigned)npairs, 256, 0, s>>>(Wc, Tot, Wf, docs, sync + npairs, k, d, f);
+    k_chain_fixup<T><<<(unsigned)npairs, 256, 0, s>>>(Wc, Tot, Wf, docs, sync + npairs, k, d, f, inclusive);
     return hipGetLastError();
   }
   const int64_t df = (int64_t)d * f;
@@ -1747,7 +1767,7 @@ hipError_t launch_state_copy(const float* Winit, float* Wf, T* Wsh, int B, int64
                                            const uint8_t*, const float*, hipStream_t, bool);                      \
   template hipError_t launch_chunk_update_scan<T>(const T*, const T*, const T*, T*, float*, T*, float*, int,      \
                                                   int, int, int, int, int, const uint8_t*, const float*,          \
-                                                  hipStream_t, int);                                              \
+                                                  hipStream_t, int, bool);                                        \
   template hipError_t launch_apply<T>(const T*, const T*, int64_t, int64_t, T*, int, int, int, int, int, float,   \
                                       hipStream_t, bool);                                                         \
   template hipError_t launch_scale<T>(const T*, T*, int64_t, float, hipStream_t, const uint8_t*, int, int, int);  \

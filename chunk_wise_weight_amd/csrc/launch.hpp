@@ -29,12 +29,14 @@ hipError_t launch_chunk_scan(const float* dW, const T* W0, T* Wc, float* Wf, int
                              const uint8_t* docs, const float* Winit, hipStream_t s, bool inclusive = false);
 // Operand layouts of the fused update-scan: the token-contiguous copies Zt
 // [B, f, n] and Vt [B, d, n]; Z [B, n, f] and V [B, n, d] as they are; the
-// latter with the chunks scanned last to first.
+// latter with the chunks scanned last to first.  inclusive (token-contiguous
+// layout, S <= 2): Wc[b, c] is the state after chunk c's own step, W_{c+1}
+// (the update-then-apply order), and no initial state is written.
 constexpr int kScanTokenContiguous = 0, kScanRowMajor = 1, kScanRowMajorReversed = 2;
 template <typename T>
 hipError_t launch_chunk_update_scan(const T* Zt, const T* Vt, const T* W0, T* Wc, float* Wf, T* Wp, float* Tot,
                                     int B, int n, int d, int f, int C, int S, const uint8_t* docs, const float* Winit,
-                                    hipStream_t s, int layout = kScanTokenContiguous);
+                                    hipStream_t s, int layout = kScanTokenContiguous, bool inclusive = false);
 
 // Number of sequence segments the fused update-scan runs side by side (a
 // segment count divides the chunk count), by a two-term cost model: the K loop

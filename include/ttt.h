@@ -212,13 +212,14 @@ typedef struct {
    * review's section on the order of the two operations): chunk c's step is
    * taken first and the chunk is applied with the state after it, so its
    * outputs see its own targets -- the layer is then not causal inside a
-   * chunk, for non-causal uses.  W_final is the same in both orders.  With
-   * the dot objective this runs the materialised plan: mode TTT_MODE_DOT_SCAN
-   * (its scan writes the states after each chunk), with that mode's
-   * workspace; TTT_MODE_DOT gives TTT_ERR_UNSUPPORTED.  The MSE objective
-   * applies each chunk a second time, after its step (one more apply's work).
-   * Not with W_states (TTT_ERR_UNSUPPORTED): the backward passes take the
-   * apply-then-update order.  Other values: TTT_ERR_ARG. */
+   * chunk, for non-causal uses.  W_final is the same in both orders.  Dot
+   * objective: the scans write the state after each chunk's step instead of
+   * the one before it (TTT_MODE_DOT runs its fused scan in one or two
+   * sequence segments then, never four), with the mode's usual workspace.
+   * The MSE objective applies each chunk a second time, after its step (one
+   * more apply's work).  Not with W_states (TTT_ERR_UNSUPPORTED): the
+   * backward passes take the apply-then-update order.  Other values:
+   * TTT_ERR_ARG. */
   int update_first;
 } ttt_layer_options;
 

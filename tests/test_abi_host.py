@@ -375,7 +375,7 @@ def test_forward_rejects_misaligned_kept_states():
 
 
 def test_update_first_validation():
-    # the update-then-apply order: 0/1 only, not with the fused dot plan nor with kept states
+    # the update-then-apply order: 0/1 only, and not with kept states
     lib = cw.lib()
     s = cw.InplaceShape(1, 2048, 256, 512, 256, 4)
     out = ctypes.c_size_t(0)
@@ -388,12 +388,13 @@ def test_update_first_validation():
                                             _fake(), _fake(), _fake(), 1 << 40, None)
 
     assert call(cw.TTT_MODE_MSE, cw.LayerOptions(None, 0, None, None, None, None, 2)) == cw.TTT_ERR_ARG
-    assert call(cw.TTT_MODE_DOT, cw.LayerOptions(None, 0, None, None, None, None, 1)) == cw.TTT_ERR_UNSUPPORTED
-    assert call(cw.TTT_MODE_MSE, cw.LayerOptions(None, 0, None, None, _fake(), None, 1)) == cw.TTT_ERR_UNSUPPORTED
+    assert call(cw.TTT_MODE_DOT, cw.LayerOptions(None, 0, None, None, None, None, -1)) == cw.TTT_ERR_ARG
+    for mode in (cw.TTT_MODE_DOT, cw.TTT_MODE_DOT_SCAN, cw.TTT_MODE_MSE):
+        assert call(mode, cw.LayerOptions(None, 0, None, None, _fake(), None, 1)) == cw.TTT_ERR_UNSUPPORTED
     lw = [_fake() for _ in range(7)]      # H, X0, W_gate, W_up, W_down0, W_target, conv_w
-    opts = cw.LayerOptions(None, 0, None, None, None, None, 1)
+    opts = cw.LayerOptions(None, 0, None, None, None, None, 3)
     assert lib.ttt_chunk_apply_update_ex(ctypes.byref(s), cw.TTT_BF16, cw.TTT_MODE_DOT, 0.1, *lw, ctypes.byref(opts),
-                                         _fake(), _fake(), _fake(), 1 << 40, None) == cw.TTT_ERR_UNSUPPORTED
+                                         _fake(), _fake(), _fake(), 1 << 40, None) == cw.TTT_ERR_ARG
 
 
 def test_lact_validation():

@@ -165,14 +165,29 @@ def test_segmented_update_scan(dtype, B, n, d, f, C, segments):
             assert rel(Wcs[c], Wc_ref) < STEP_TOL[dtype], (b, c)
 
 
+def test_core_update_first_on_a_four_segment_shape():
+    """A state of 64 tiles with 8 chunks, which the fused dot plan would scan as four sequence segments: in the
+    update-then-apply order it runs one (the states after each step), against the oracle in that order."""
+    B, n, d, f, C, eta = 1, 2048, 1024, 4096, 256, 0.02
+    Z, V, W0 = _zv("bf16", B, n, d, f, 43)
+    O, Wf = cw.ttt_core_apply_update(Z.cuda(), V.cuda(), W0.cuda(), C, eta, "dot", update_first=True)
+    Oa, Wa = cw.ttt_core_apply_update(Z.cuda(), V.cuda(), W0.cuda(), C, eta, "dot")
+    torch.cuda.synchronize()
+    Oref, Wref = orc.chunk_apply_update(f64(Z[0]), f64(V[0]), f64(W0), C, eta, "dot", update_first=True)
+    assert rel(f64(O[0]), Oref) < TOL["bf16"]
+    assert rel(f64(Wf[0]), Wref) < TOL["bf16"] and rel(f64(Wa[0]), Wref) < TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("fallback", [False, True])
-def test_chained_segments_with_documents(dtype, fallback, monkeypatch):
+@pytest.mark.parametrize("update_first", [False, True])
+def test_chained_segments_with_documents(dtype, fallback, update_first, monkeypatch):
     """Two chained segments (260 state tiles, 8 chunks, segment 1 from chunk 4) on the chunk loop given Z and V^
     (dot objective, fused plan), with documents starting further into segment 1 (row 0), at its first chunk (row
     1) and one chunk into it (row 2), and none (row 3), against the oracle run per document.  With the wait
     disabled (TTT_UPDATE_SCAN_WAIT_US=-1) every segment-1 tile keeps partial states and the fix-up kernel
-    completes it: the same results up to rounding."""
+    completes it: the same results up to rounding.  update_first: the scan writes the states after each chunk's step
+    (the chained segment then also needs the first segment's end state when a document starts one chunk in)."""
     B, n, d, f, C, eta = 4, 2048, 2560, 6656, 256, 0.02
     k = n // C
     starts = np.zeros((B, k), dtype=np.uint8)
@@ -183,19 +198,21 @@ def test_chained_segments_with_documents(dtype, fallback, monkeypatch):
     g = (Z.cuda(), V.cuda(), W0.cuda())
     if fallback:
         monkeypatch.setenv("TTT_UPDATE_SCAN_WAIT_US", "-1")
-    O, Wf = cw.ttt_core_apply_update(*g, C, eta, "dot", doc_starts=torch.from_numpy(starts).cuda())
+    O, Wf = cw.ttt_core_apply_update(*g, C, eta, "dot", doc_starts=torch.from_numpy(starts).cuda(),
+                                     update_first=update_first)
     torch.cuda.synchronize()
     W0n = f64(W0)
     for b in range(B):
         bounds = [0] + [c for c in range(1, k) if starts[b, c]] + [k]
         for s0, e0 in zip(bounds[:-1], bounds[1:]):
             Oref, Wref = orc.chunk_apply_update(f64(Z[b, s0 * C:e0 * C]), f64(V[b, s0 * C:e0 * C]), W0n, C, eta,
-                                                "dot")
+                                                "dot", update_first=update_first)
             assert rel(f64(O[b, s0 * C:e0 * C]), Oref) < TOL[dtype], (b, s0)
         assert rel(f64(Wf[b]), Wref) < TOL[dtype] and rel(f64(Wf[b]) - W0n, Wref - W0n) < TOL[dtype], b
     if fallback:
         monkeypatch.delenv("TTT_UPDATE_SCAN_WAIT_US")
-        O2, Wf2 = cw.ttt_core_apply_update(*g, C, eta, "dot", doc_starts=torch.from_numpy(starts).cuda())
+        O2, Wf2 = cw.ttt_core_apply_update(*g, C, eta, "dot", doc_starts=torch.from_numpy(starts).cuda(),
+                                           update_first=update_first)
         torch.cuda.synchronize()
         assert rel(f64(O), f64(O2)) < STEP_TOL[dtype] and rel(f64(Wf), f64(Wf2)) < STEP_TOL[dtype]
 
@@ -414,7 +431,7 @@ def test_layer_resumed_in_two_calls(dtype, mode):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("mode", ["dot_scan", "mse"])
+@pytest.mark.parametrize("mode", ["dot", "dot_scan", "mse"])
 def test_layer_update_first(dtype, mode):
     """The update-then-apply order (update_first): each chunk is applied with the state after its own step,
     against the oracle in that order, with every option it combines with.  Row 0 starts a document at chunk 0
@@ -453,7 +470,7 @@ def test_layer_update_first(dtype, mode):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("mode", ["dot_scan", "mse"])
+@pytest.mark.parametrize("mode", ["dot", "dot_scan", "mse"])
 def test_core_update_first(dtype, mode):
     """The chunk loop given Z and V^ in the update-then-apply order, against the oracle's sequential definition
     in that order, per row (ragged d and f, four chunks)."""
