@@ -238,7 +238,7 @@ def ttt_chunk_apply_update(H, X0, W_gate, W_up, W_down0, W_target, conv_w, chunk
     earlier call (its W_final and its last K-1 rows of X0); W_states [B, seq_len // chunk, d, f] (dtype) to keep
     the per-chunk states of the dot objective for ttt_core_backward; update_mask, a uint8 (or bool) device tensor
     [B, seq_len // chunk] whose zero entries mark chunks that are applied without updating the state;
-    update_first, each chunk's step taken before its apply (modes "dot_scan" and "mse")."""
+    update_first, each chunk's step taken before its apply (every mode; not with W_states)."""
     B, n, d = H.shape
     f = W_gate.shape[0]
     K = conv_w.shape[1]
