@@ -1,7 +1,8 @@
 """The layer calls captured into HIP graphs (torch.cuda.CUDAGraph drives the capture).
 
-The library enqueues kernels only -- no allocation, copy or memset -- and the LaCT call given a side stream adds
-an event fork and join with it, which a capture records as parallel branches.  The backward entry points (the dot and MSE
+The library enqueues kernels only -- no allocation, copy or memset (the chained update-scan clears its flags with a
+kernel) -- and the LaCT call given a side stream adds an event fork and join with it, which a capture records as
+parallel branches.  The backward entry points (the dot and MSE
 chunk loops, the whole dot layer, the LaCT layer) are captured the same way.  Each graph is replayed three times with
 the outputs clobbered, eager calls and synchronisations in between, and every replay must reproduce the eager
 call's bits.
@@ -16,8 +17,12 @@ pytestmark = pytest.mark.gpu
 
 
 def _inplace(mode):
-    cfg = ti.InplaceConfig("graph", 2, 1024, 264, 392, 256, 0.05 if mode == "dot" else 0.5, mode, "bf16", conv_k=4,
-                           seed=13)
+    if mode == "dot_chained":       # a 260-tile state: the fused scan runs two chained segments (flags zeroed per call)
+        cfg = ti.InplaceConfig("graph", 1, 1024, 2560, 6656, 256, 0.02, "dot", "bf16", conv_k=4, seed=29)
+    else:
+        cfg = ti.InplaceConfig("graph", 2, 1024, 264, 392, 256, 0.05 if mode == "dot" else 0.5, mode, "bf16",
+                               conv_k=4, seed=13)
+    mode = cfg.mode
     g = {k: v.cuda() for k, v in ti.inplace_inputs(cfg).items()}
     args = (g["H"], g["X0"], g["W_gate"], g["W_up"], g["W_down0"], g["W_target"], g["conv_w"], cfg.chunk, cfg.eta,
             mode)
@@ -52,8 +57,8 @@ def _backward(kind):
     return lambda: fn(g["Z"], g["Vhat"], g["W_down0"], g["dO"], cfg.chunk, cfg.eta)
 
 
-@pytest.mark.parametrize("kind", ["dot", "mse", "lact", "lact_side", "backward", "mse_backward", "layer_backward",
-                                  "lact_backward"])
+@pytest.mark.parametrize("kind", ["dot", "dot_chained", "mse", "lact", "lact_side", "backward", "mse_backward",
+                                  "layer_backward", "lact_backward"])
 def test_graph_replays_match_eager(kind):
     call = (_lact_backward() if kind == "lact_backward" else _lact(kind == "lact_side") if kind.startswith("lact")
             else _backward(kind) if "backward" in kind else _inplace(kind))
