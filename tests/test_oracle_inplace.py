@@ -1026,6 +1026,26 @@ def test_update_first_dot_closed_form():
     np.testing.assert_array_equal(Wu, Wa)
 
 
+def test_update_first_mse_closed_form():
+    """MSE objective, update first: W_{c+1} = W_c - (eta/C) R_c^T Z_c with R_c = Z_c W_c^T - V^_c, so
+    O_c = Z_c W_{c+1}^T = (apply-then-update output) - (eta/C) (Z_c Z_c^T) R_c: the chunk's own residual through its
+    token Gram matrix.  R_c is formed here from the apply-then-update outputs, which are Z_c W_c^T; W_final is the
+    same in both orders.  The ragged last chunk divides by its own length."""
+    rng = _rng(92)
+    n, C, d, f, eta = 14, 4, 3, 5, 0.7
+    Z, V = rng.standard_normal((n, f)) * 0.5, rng.standard_normal((n, d))
+    W0 = rng.standard_normal((d, f)) * 0.4
+    Oa, Wa = orc.chunk_apply_update(Z, V, W0, C, eta, "mse")
+    Ou, Wu = orc.chunk_apply_update(Z, V, W0, C, eta, "mse", update_first=True)
+    want = Oa.copy()
+    for s0 in range(0, n, C):
+        Zc, Vc = Z[s0:s0 + C], V[s0:s0 + C]
+        Rc = Oa[s0:s0 + C] - Vc
+        want[s0:s0 + C] -= eta / len(Zc) * (Zc @ Zc.T) @ Rc
+    np.testing.assert_allclose(Ou, want, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(Wu, Wa)
+
+
 @pytest.mark.parametrize("mode", ["dot", "mse"])
 def test_update_first_layer_equals_truncated_final_states(mode):
     """The layer with update_first: chunk c's outputs are Z_c times the W_final of the apply-then-update layer
