@@ -461,18 +461,54 @@ struct Staged {
   __device__ __forceinline__ void put1(int r, int col, float v) const {
     *reinterpret_cast<TO*>(base + off(r, col)) = from_f32<TO>(v);
   }
-  // Rows [0, nrows) out to global memory; dst(r, col) is the address of element
-  // col of row r (col a multiple of EPP, 16-byte aligned) or nullptr to skip.
-  // STREAM: non-temporal stores, for data that is not read again soon.
-  template <int NT, class Dst, bool STREAM = false>
+  // Rows [0, nrows) out to global memory, nrows <= MAXROWS (the rows the
+  // staging area holds); dst(r, col) is the address of element col of row r
+  // (col a multiple of EPP, 16-byte aligned) or nullptr to skip.  Thread x
+  // copies piece x % PPR of rows x / PPR, x / PPR + NT / PPR, ...; it reads
+  // BATCH of its pieces from LDS before storing any, so that one LDS wait
+  // covers a batch (a loop of read, wait, store per piece leaves the wave
+  // idle for the LDS latency at every piece).  A wave's stores cover whole
+  // 128-byte lines.  STREAM: non-temporal stores, for data that is not read
+  // again soon.  BATCH = 0: one piece at a time in a loop, for kernels that
+  // keep their accumulators live across the copy-out and have no registers
+  // to spare.
+  template <int NT, int MAXROWS, bool STREAM = false, int BATCH = 8, class Dst>
   __device__ __forceinline__ void flush(int nrows, Dst&& dst) const {
-    for (int idx = threadIdx.x; idx < nrows * PPR; idx += NT) {
-      const int r = idx / PPR, c = idx - r * PPR;
-      TO* p = dst(r, c * EPP);
-      if (p == nullptr) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(base + r * RB + ((c ^ (r & 15)) << 4));
-      if constexpr (STREAM) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-      else *reinterpret_cast<u32x4*>(p) = v;
+    if constexpr (BATCH == 0) {
+      for (int idx = threadIdx.x; idx < nrows * PPR; idx += NT) {
+        const int r = idx / PPR, c = idx - r * PPR;
+        TO* p = dst(r, c * EPP);
+        if (p == nullptr) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(base + r * RB + ((c ^ (r & 15)) << 4));
+        if constexpr (STREAM) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+        else *reinterpret_cast<u32x4*>(p) = v;
+      }
+    } else {
+      static_assert(NT % PPR == 0, "a thread's pieces share one column slot");
+      constexpr int RS = NT / PPR;                        // rows between a thread's pieces
+      static_assert(MAXROWS % RS == 0, "whole rounds of pieces");
+      constexpr int ITER = MAXROWS / RS;                  // pieces per thread
+      constexpr int NB = BATCH < ITER ? BATCH : ITER;
+      static_assert(ITER % NB == 0, "whole batches");
+      const int c = (int)threadIdx.x % PPR, r0 = (int)threadIdx.x / PPR;
+#pragma unroll
+      for (int i0 = 0; i0 < ITER; i0 += NB) {
+        u32x4 v[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int r = r0 + (i0 + u) * RS;
+          v[u] = *reinterpret_cast<const u32x4*>(base + r * RB + ((c ^ (r & 15)) << 4));
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int r = r0 + (i0 + u) * RS;
+          if (r >= nrows) continue;
+          TO* p = dst(r, c * EPP);
+          if (p == nullptr) continue;
+          if constexpr (STREAM) __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(p));
+          else *reinterpret_cast<u32x4*>(p) = v[u];
+        }
+      }
     }
   }
   // Transposed copy-out: output row c (c < ncols) is column c of the staged

@@ -357,7 +357,7 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z(const T* __restrict__ H, const T* __restr
       for (int jj = 0; jj < 2; ++jj)
         st.put4(jl + 16 * jj, G::acc_p(i, 0), acc[i][jj][0], acc[i][jj][1], acc[i][jj][2], acc[i][jj][3]);
     __syncthreads();
-    st.template flush<G::NT>(jn, [&](int r, int col) -> T* {
+    st.template flush<G::NT, G::BQ / 2, false, 0>(jn, [&](int r, int col) -> T* {
       if (col >= tn) return nullptr;
       const int64_t tok = t0 + col, b = tok / n;
       return Zt + (b * f + j0 + r) * (int64_t)n + (tok - b * n);
@@ -374,7 +374,7 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z(const T* __restrict__ H, const T* __restr
 #pragma unroll
         for (int e = 0; e < 4; ++e) sz.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj][e]);
     __syncthreads();
-    sz.template flush<G::NT>(tn, [&](int r, int col) -> T* {
+    sz.template flush<G::NT, G::BP, false, 0>(tn, [&](int r, int col) -> T* {
       return col < jn ? Z + (t0 + r) * f + j0 + col : nullptr;
     });
   }
@@ -420,6 +420,7 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z_bwd(const T* __restrict__ H, const T* __r
   // memory element by element and the two results share the LDS in turn.
   constexpr bool kStageDz = sizeof(T) == 2;
   constexpr int kHalf = G::BP * (G::BQ / 2) * (int)sizeof(T);
+  constexpr int kFlushBatch = sizeof(T) == 2 ? 8 : 0;          // fp32: no registers to spare
   const Staged<T, G::BQ / 2> sdz{smem}, sda{smem + (kStageDz ? kHalf : 0)};
   if constexpr (kStageDz) {
     constexpr int PPR = (G::BQ / 2) * (int)sizeof(T) / 16;          // 16-byte pieces per row
@@ -457,7 +458,7 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z_bwd(const T* __restrict__ H, const T* __r
   }
   __syncthreads();
   // dA out as whole rows of G; then dU staged over the dZ tile (read by all waves before the barrier above)
-  sda.template flush<G::NT>(tn, [&](int r, int col) -> T* {
+  sda.template flush<G::NT, G::BP, false, kFlushBatch>(tn, [&](int r, int col) -> T* {
     return col < jn ? Gout + (t0 + r) * ldg + j0 + col : nullptr;
   });
   if constexpr (!kStageDz) __syncthreads();
@@ -468,7 +469,7 @@ TTT_GEMM_KERNEL(Wide) void k_produce_z_bwd(const T* __restrict__ H, const T* __r
 #pragma unroll
       for (int e = 0; e < 4; ++e) sdz.put1(G::acc_p(i, 0) + e, jl + 16 * jj, acc[i][jj + 2][e]);
   __syncthreads();
-  sdz.template flush<G::NT>(tn, [&](int r, int col) -> T* {
+  sdz.template flush<G::NT, G::BP, false, kFlushBatch>(tn, [&](int r, int col) -> T* {
     return col < jn ? Gout + (t0 + r) * ldg + f + j0 + col : nullptr;
   });
 }
@@ -524,7 +525,7 @@ TTT_GEMM_KERNEL(Wide) void k_produce_vhat(const T* __restrict__ Y, const T* __re
                 sc[i] * acc[i][j][3]);
     }
     __syncthreads();
-    st.template flush<G::NT>(RPP, [&](int r, int col) -> T* {
+    st.template flush<G::NT, RPP, false, 0>(RPP, [&](int r, int col) -> T* {
       const int o = o0 + ps * RPP + r;
       if (o >= d || col >= tn) return nullptr;
       const int64_t tok = t0 + col, b = tok / n;
@@ -594,7 +595,7 @@ __device__ __forceinline__ void stage_state(const Acc& acc, TO* __restrict__ out
     auto dst = [&](int r, int col) -> TO* {
       return col < jn ? out + (int64_t)(i0 + ps * RPP + r) * f + j0 + col : nullptr;
     };
-    st.template flush<G::NT, decltype(dst)&, STREAM>(max(0, min(RPP, in_ - ps * RPP)), dst);
+    st.template flush<G::NT, RPP, STREAM, 0>(max(0, min(RPP, in_ - ps * RPP)), dst);
     __syncthreads();
   }
 }
@@ -1073,7 +1074,7 @@ TTT_GEMM_KERNEL(Wide) void k_apply(const T* __restrict__ Zt, const T* __restrict
                 oscale * acc[i][j][3]);
     }
     __syncthreads();
-    st.template flush<G::NT>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
+    st.template flush<G::NT, RPP, false, 0>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
       return col < in_ ? O + (row0 + ps * RPP + r) * d + i0 + col : nullptr;
     });
     __syncthreads();
@@ -1147,7 +1148,7 @@ TTT_GEMM_KERNEL(Wide) void k_dz(const T* __restrict__ dO, const T* __restrict__ 
       for (int i = 0; i < G::NPB; ++i) st.put4(q, G::acc_p(i, 0), acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
     }
     __syncthreads();
-    st.template flush<G::NT>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
+    st.template flush<G::NT, RPP>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
       return col < jn ? dZ + (row0 + ps * RPP + r) * f + j0 + col : nullptr;
     });
     __syncthreads();
@@ -1333,7 +1334,7 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
         }
       }
       __syncthreads();
-      st.template flush<G::NT>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
+      st.template flush<G::NT, RPP, false, 0>(max(0, min(RPP, tn - ps * RPP)), [&](int r, int col) -> T* {
         return col < in_ ? O + (row0 + ps * RPP + r) * d + i0 + col : nullptr;
       });
       __syncthreads();

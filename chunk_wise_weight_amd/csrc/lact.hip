@@ -149,7 +149,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd1(const T* __restrict__ q, const T* __restr
   };
   auto flush = [&](char* base, T* dst) __attribute__((always_inline)) {   // dst: [C, m] block of this bh
     const ST st{base};
-    st.template flush<G::NT>(tn, [&](int r, int col) -> T* {
+    st.template flush<G::NT, G::BQ>(tn, [&](int r, int col) -> T* {
       return col < jn ? dst + (int64_t)(r0 + r) * m + j0 + col : nullptr;
     });
   };
@@ -264,7 +264,7 @@ TTT_GEMM_KERNEL(Wide) void k_lact_fwd2(const T* __restrict__ Hh, const T* __rest
     }
     __syncthreads();
     const int rows = max(0, min(RPP, tn - ps * RPP));
-    st.template flush<G::NT>(rows, [&](int rr, int col) -> T* {
+    st.template flush<G::NT, RPP>(rows, [&](int rr, int col) -> T* {
       return col < in_ ? base + (int64_t)(r0 + ps * RPP + rr) * dh + i0 + col : nullptr;
     });
     __syncthreads();
