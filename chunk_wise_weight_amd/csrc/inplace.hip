@@ -573,7 +573,9 @@ __device__ __forceinline__ void store_state(const Acc& acc, TO* __restrict__ out
 // j = P) is staged in BUFB bytes at buf, in as many passes over its rows as
 // needed, and written out as whole 16-byte pieces along rows (non-temporal
 // stores with STREAM).  Every wave must call it; it ends with a barrier.
-template <class G, int BUFB, typename TO, class Acc, bool STREAM = false>
+// BATCH: the copy-out's LDS read batch (0: one piece at a time, for callers
+// inside a K loop, whose accumulators stay live).
+template <class G, int BUFB, typename TO, class Acc, bool STREAM = false, int BATCH = 0>
 __device__ __forceinline__ void stage_state(const Acc& acc, TO* __restrict__ out, char* buf, int j0, int i0, int d,
                                             int f) {
   static_assert(G::GPB == 1, "one accumulator group per block");
@@ -595,7 +597,7 @@ __device__ __forceinline__ void stage_state(const Acc& acc, TO* __restrict__ out
     auto dst = [&](int r, int col) -> TO* {
       return col < jn ? out + (int64_t)(i0 + ps * RPP + r) * f + j0 + col : nullptr;
     };
-    st.template flush<G::NT, RPP, STREAM, 0>(max(0, min(RPP, in_ - ps * RPP)), dst);
+    st.template flush<G::NT, RPP, STREAM, BATCH>(max(0, min(RPP, in_ - ps * RPP)), dst);
     __syncthreads();
   }
 }
@@ -1436,9 +1438,9 @@ TTT_GEMM_KERNEL(Wide) void k_mse_update(const T* __restrict__ Zt, const T* __res
   });
   mainloop<T, G>(op, oq, (int)((kbytes + 127) / 128), acc, smem, NoHook{});
 
-  stage_state<G, G::Smem, float, decltype(acc), true>(acc, ws, smem, j0, i0, d, f);
+  stage_state<G, G::Smem, float, decltype(acc), true, 8>(acc, ws, smem, j0, i0, d, f);
   if (Wsh != nullptr)
-    stage_state<G, G::Smem, T, decltype(acc), false>(acc, Wsh + (int64_t)b * d * f, smem, j0, i0, d, f);
+    stage_state<G, G::Smem, T, decltype(acc), false, 8>(acc, Wsh + (int64_t)b * d * f, smem, j0, i0, d, f);
 }
 
 // ------------------------------------------------------------------ launchers
