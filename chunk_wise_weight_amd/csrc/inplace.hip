@@ -1367,24 +1367,43 @@ TTT_GEMM_KERNEL(Wide) void k_mse_apply(const T* __restrict__ Zt, const T* __rest
       }
       __syncthreads();
       const int rows = max(0, min(RPP, in_ - ps * RPP));
-      for (int idx = threadIdx.x; idx < rows * SPANS; idx += G::NT) {
-        const int r = idx / SPANS, t = (idx - r * SPANS) * 8;
-        if (t >= tn) continue;                          // tn % 8 == 0
-        const int64_t ch = ps * RPP + r;
-        const f32x4 o0 = *reinterpret_cast<const f32x4*>(smem + st.off(r, t));
-        const f32x4 o1 = *reinterpret_cast<const f32x4*>(smem + st.off(r, t + 4));
-        const f32x4 v0 = load4(vt + ch * n + t), v1 = load4(vt + ch * n + t + 4);
-        T* dst = rt + ch * C_ + t;
-        if constexpr (GEN) {
-          store4(dst, rscale * o0[0] + vscale * v0[0], rscale * o0[1] + vscale * v0[1],
-                 rscale * o0[2] + vscale * v0[2], rscale * o0[3] + vscale * v0[3]);
-          store4(dst + 4, rscale * o1[0] + vscale * v1[0], rscale * o1[1] + vscale * v1[1],
-                 rscale * o1[2] + vscale * v1[2], rscale * o1[3] + vscale * v1[3]);
-        } else {
-          store4(dst, rscale * (o0[0] - v0[0]), rscale * (o0[1] - v0[1]), rscale * (o0[2] - v0[2]),
-                 rscale * (o0[3] - v0[3]));
-          store4(dst + 4, rscale * (o1[0] - v1[0]), rscale * (o1[1] - v1[1]), rscale * (o1[2] - v1[2]),
-                 rscale * (o1[3] - v1[3]));
+      // KB spans per thread and trip, their V^ loads all issued before any
+      // is used (one memory latency per trip rather than per span)
+      constexpr int KB = 4;
+      for (int i0s = threadIdx.x; i0s < rows * SPANS; i0s += KB * G::NT) {
+        f32x4 v0[KB], v1[KB];
+        int rr[KB], tt[KB];
+        bool ok[KB];
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+          const int idx = i0s + k * G::NT;
+          rr[k] = idx / SPANS;
+          tt[k] = (idx - rr[k] * SPANS) * 8;
+          ok[k] = idx < rows * SPANS && tt[k] < tn;     // tn % 8 == 0
+          if (ok[k]) {
+            const T* vp = vt + (int64_t)(ps * RPP + rr[k]) * n + tt[k];
+            v0[k] = load4(vp);
+            v1[k] = load4(vp + 4);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+          if (!ok[k]) continue;
+          const int r = rr[k], t = tt[k];
+          const f32x4 o0 = *reinterpret_cast<const f32x4*>(smem + st.off(r, t));
+          const f32x4 o1 = *reinterpret_cast<const f32x4*>(smem + st.off(r, t + 4));
+          T* dst = rt + (int64_t)(ps * RPP + r) * C_ + t;
+          if constexpr (GEN) {
+            store4(dst, rscale * o0[0] + vscale * v0[k][0], rscale * o0[1] + vscale * v0[k][1],
+                   rscale * o0[2] + vscale * v0[k][2], rscale * o0[3] + vscale * v0[k][3]);
+            store4(dst + 4, rscale * o1[0] + vscale * v1[k][0], rscale * o1[1] + vscale * v1[k][1],
+                   rscale * o1[2] + vscale * v1[k][2], rscale * o1[3] + vscale * v1[k][3]);
+          } else {
+            store4(dst, rscale * (o0[0] - v0[k][0]), rscale * (o0[1] - v0[k][1]), rscale * (o0[2] - v0[k][2]),
+                   rscale * (o0[3] - v0[k][3]));
+            store4(dst + 4, rscale * (o1[0] - v1[k][0]), rscale * (o1[1] - v1[k][1]), rscale * (o1[2] - v1[k][2]),
+                   rscale * (o1[3] - v1[k][3]));
+          }
         }
       }
       __syncthreads();
